@@ -1,0 +1,341 @@
+/*
+ * oracle.c -- plain, slow CPU reference of the sparse front end of a CTR ranking model.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the tests, the package smoke check and the benchmark's
+ * CPU-baseline leg may load this library.  It shares no code, header, table or helper with
+ * the HIP library; both sides read the same seeded inputs and nothing else.
+ *
+ * Every floating-point result is accumulated in double precision (fp32 inputs widen
+ * exactly; fp32 x fp32 products are exact in fp64).  Beside each floating output the oracle
+ * also returns a magnitude M = sum of |terms| (propagated from input magnitudes when those
+ * are given), so that a result y is checked as |y_gpu - y| <= rtol * M.  This is the
+ * textbook forward-error form of a floating-point sum, |s_hat - s| <= gamma_(n-1) * sum|x_i|.
+ *
+ * Sources (web pages, cited by title and section):
+ *   [DHEN]  "DHEN" notes (calwoo.github.io), section 2.1 "Feature Processing Layer":
+ *           each categorical term has a trainable d-dim vector; the dense features become
+ *           one d-dim vector; the slot vectors are concatenated into X0 = (x_1..x_m).
+ *           Section 3.1 "AdvancedDLRM" and Solution 2: inner products of all embedding
+ *           pairs, the vector (s_ij)_{i<j} of length C(m,2), concatenated with the dense
+ *           features; the squared-norm identity for the sum of all pair dots.
+ *   [TN]    "How TensorNet Supercharges Sparse Feature Training on TensorFlow", section
+ *           "Core Optimizations": collect the batch's IDs, sort them, give each a contiguous
+ *           index (the virtual sparse feature), fetch the rows into a batch-sized matrix;
+ *           section "Synchronous Architecture": only features present in the batch move.
+ *   [DLRM]  "Meta DLRM" (upskillscore.com), section 02: the interaction is the dot product
+ *           between all pairs of embedding vectors and the processed dense features.
+ * Readings where the pages are silent (sum pooling, strict i > j pair order, sum of
+ * gradients over the batch, RNE storage rounding) follow the plain definitions below.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* ------------------------------------------------------------------ threads */
+void orc_set_threads(int n) {
+#ifdef _OPENMP
+  if (n > 0) omp_set_num_threads(n);
+#else
+  (void)n;
+#endif
+}
+
+int orc_get_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}
+
+/* ------------------------------------------------------------------ rounding */
+/* Round a double to the nearest bfloat16 value (8 significant bits, exponent range of
+ * binary32), ties to even, returned as a double.  Written from the IEEE-754 definition:
+ * x = m * 2^e with 0.5 <= |m| < 1, keep 8 bits of m with round-half-even (rint in the
+ * default rounding mode), below the normal range the quantum stays 2^-133. */
+double orc_round_bf16(double x) {
+  if (x == 0.0 || isnan(x) || isinf(x)) return x;
+  int e;
+  frexp(x, &e);
+  int q = e - 8;                 /* exponent of the last kept bit */
+  if (q < -133) q = -133;        /* subnormal bf16 quantum */
+  double r = ldexp(rint(ldexp(x, -q)), q);
+  if (fabs(r) > 3.3895313892515355e38) r = copysign(INFINITY, x); /* beyond bf16 max */
+  return r;
+}
+
+/* Round a double to binary32, ties to even (C conversion in the default rounding mode). */
+double orc_round_f32(double x) { return (double)(float)x; }
+
+/* ------------------------------------------------------------------ table fill */
+/* splitmix64 (Steele, Lea, Flood, "Fast splittable pseudorandom number generators",
+ * OOPSLA 2014): the state advances by the golden-ratio increment, and the output is the
+ * state passed through two xor-shift-multiply rounds and a final xor-shift. */
+uint64_t orc_splitmix64_next(uint64_t* state) {
+  uint64_t z = (*state += 0x9E3779B97F4A7C15ull);
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  return z ^ (z >> 31);
+}
+
+/* Table element (global_row, col): one splitmix64 output from state seed ^ (row*dim+col);
+ * its top 24 bits give u in [0,1); x = fp32(2u-1) * fp32(1/sqrt(rows_t)) in binary32;
+ * bf16 storage rounds x to nearest-even.  Returns the stored value. */
+double orc_table_value(uint64_t seed, int64_t global_row, int64_t col, int32_t dim,
+                       int64_t rows_t, int32_t bf16) {
+  uint64_t st = seed ^ (uint64_t)(global_row * (int64_t)dim + col);
+  uint64_t v = orc_splitmix64_next(&st);
+  double u = (double)(v >> 40) * (1.0 / 16777216.0);
+  float a = (float)(1.0 / sqrt((double)rows_t));
+  float s = (float)(2.0 * u - 1.0);
+  float x = s * a;
+  return bf16 ? orc_round_bf16((double)x) : (double)x;
+}
+
+typedef struct {
+  const float* data;        /* host copy of the table values, or NULL: regenerate */
+  uint64_t seed;
+  const int64_t* row_base;  /* [num_tables + 1] */
+  int32_t num_tables;
+  int32_t dim;
+  int32_t bf16;
+} orc_table;
+
+static int64_t rows_of_key(const orc_table* tb, int64_t key) {
+  for (int32_t t = 0; t < tb->num_tables; ++t)
+    if (key >= tb->row_base[t] && key < tb->row_base[t + 1])
+      return tb->row_base[t + 1] - tb->row_base[t];
+  return -1;
+}
+
+static double tval(const orc_table* tb, int64_t key, int64_t col) {
+  if (tb->data) return (double)tb->data[key * (int64_t)tb->dim + col];
+  return orc_table_value(tb->seed, key, col, tb->dim, rows_of_key(tb, key), tb->bf16);
+}
+
+/* Fill rows `keys[0..n)` of the described table into out[n][dim] (as stored values). */
+void orc_table_rows(uint64_t seed, const int64_t* row_base, int32_t num_tables, int32_t dim,
+                    int32_t bf16, const int64_t* keys, int64_t n, float* out) {
+  orc_table tb = {NULL, seed, row_base, num_tables, dim, bf16};
+#pragma omp parallel for schedule(static)
+  for (int64_t r = 0; r < n; ++r)
+    for (int64_t c = 0; c < dim; ++c) out[r * dim + c] = (float)tval(&tb, keys[r], c);
+}
+
+/* ------------------------------------------------------------------ a1: keys */
+/* key[i] = row_base[t] + (modulus > 0 ? floor_mod(id[i], modulus) : id[i]) for the
+ * occurrence i inside bag (t, b), bags table-major with `batch` bags per table. */
+void orc_form_keys(const int64_t* ids, const int64_t* offsets, int64_t num_tables,
+                   int64_t batch, const int64_t* row_base, int64_t modulus, int64_t* keys) {
+  for (int64_t t = 0; t < num_tables; ++t)
+    for (int64_t b = 0; b < batch; ++b) {
+      int64_t s = t * batch + b;
+      for (int64_t i = offsets[s]; i < offsets[s + 1]; ++i) {
+        int64_t id = ids[i];
+        if (modulus > 0) {
+          id %= modulus;
+          if (id < 0) id += modulus;
+        }
+        keys[i] = (row_base ? row_base[t] : 0) + id;
+      }
+    }
+}
+
+/* ------------------------------------------------------------------ a2: unique */
+typedef struct {
+  int64_t key;
+  int64_t idx;
+} kv;
+
+static int kv_cmp(const void* a, const void* b) {
+  const kv* x = (const kv*)a;
+  const kv* y = (const kv*)b;
+  if (x->key != y->key) return x->key < y->key ? -1 : 1;
+  return x->idx < y->idx ? -1 : (x->idx > y->idx);
+}
+
+/* [TN] "Core Optimizations": sort the batch's IDs and give each distinct ID a contiguous
+ * index.  Sorting (key, occurrence) pairs makes the order total, hence stable.
+ *   uniq[u]      distinct keys, ascending (signed)
+ *   inverse[i]   u with uniq[u] == key[i]
+ *   perm[p]      occurrence at sorted position p (stable argsort)
+ *   seg[u]       first sorted position of uniq[u]; seg[U] = n
+ * Returns U. */
+int64_t orc_unique(const int64_t* keys, int64_t n, int64_t* uniq, int32_t* inverse,
+                   int32_t* perm, int32_t* seg) {
+  if (n == 0) {
+    if (seg) seg[0] = 0;
+    return 0;
+  }
+  kv* a = (kv*)malloc((size_t)n * sizeof(kv));
+  for (int64_t i = 0; i < n; ++i) {
+    a[i].key = keys[i];
+    a[i].idx = i;
+  }
+  qsort(a, (size_t)n, sizeof(kv), kv_cmp);
+  int64_t u = -1;
+  for (int64_t p = 0; p < n; ++p) {
+    if (p == 0 || a[p].key != a[p - 1].key) {
+      ++u;
+      uniq[u] = a[p].key;
+      if (seg) seg[u] = (int32_t)p;
+    }
+    inverse[a[p].idx] = (int32_t)u;
+    if (perm) perm[p] = (int32_t)a[p].idx;
+  }
+  if (seg) seg[u + 1] = (int32_t)n;
+  free(a);
+  return u + 1;
+}
+
+/* ------------------------------------------------------------------ a3: gather */
+/* [TN] "Core Optimizations": fetch the batch's rows into the batch-sized matrix,
+ * E[u] = W[rows[u]]. */
+void orc_gather_rows(const float* data, uint64_t seed, const int64_t* row_base,
+                     int32_t num_tables, int32_t dim, int32_t bf16, const int64_t* rows,
+                     int64_t n, double* out) {
+  orc_table tb = {data, seed, row_base, num_tables, dim, bf16};
+#pragma omp parallel for schedule(static)
+  for (int64_t u = 0; u < n; ++u)
+    for (int64_t c = 0; c < dim; ++c) out[u * dim + c] = tval(&tb, rows[u], c);
+}
+
+/* ------------------------------------------------------------------ a4: pooling */
+/* [DHEN] 2.1: one d-dim vector per sparse feature.  Sum pooling of the bag's rows (each
+ * occurrence counted, empty bag = 0).  out and mag are [batch][num_tables][dim].
+ * Row of occurrence i: key = row_base[t] + ids[i] (ids are table-local rows here). */
+void orc_embbag_fwd(const float* data, uint64_t seed, const int64_t* row_base,
+                    int32_t num_tables, int32_t dim, int32_t bf16, const int64_t* ids,
+                    const int64_t* offsets, int64_t batch, double* out, double* mag) {
+  orc_table tb = {data, seed, row_base, num_tables, dim, bf16};
+#pragma omp parallel for schedule(dynamic, 64)
+  for (int64_t s = 0; s < (int64_t)num_tables * batch; ++s) {
+    int64_t t = s / batch, b = s % batch;
+    double* o = out + (b * num_tables + t) * dim;
+    double* m = mag + (b * num_tables + t) * dim;
+    for (int64_t c = 0; c < dim; ++c) {
+      o[c] = 0.0;
+      m[c] = 0.0;
+    }
+    for (int64_t i = offsets[s]; i < offsets[s + 1]; ++i) {
+      int64_t key = row_base[t] + ids[i];
+      for (int64_t c = 0; c < dim; ++c) {
+        double w = tval(&tb, key, c);
+        o[c] += w;
+        m[c] += fabs(w);
+      }
+    }
+  }
+}
+
+/* ------------------------------------------------------------------ a6: interaction */
+/* [DLRM] 02 and [DHEN] 3.1 / Solution 2: for each sample, the dense vector z_0 followed by
+ * the dot products <z_i, z_j> of every pair i > j (strict: C(F,2) of them), in the order
+ * of the row-major strict lower triangle, index i(i-1)/2 + j.
+ * Z, zmag: [batch][F][dim] (zmag may be NULL: |Z|); R, rmag: [batch][dim + P]. */
+void orc_interaction_fwd(const double* Z, const double* zmag, int64_t batch, int32_t F,
+                         int32_t dim, double* R, double* rmag) {
+  int64_t P = (int64_t)F * (F - 1) / 2, W = dim + P;
+#pragma omp parallel for schedule(static)
+  for (int64_t b = 0; b < batch; ++b) {
+    const double* z = Z + b * F * dim;
+    const double* zm = zmag ? zmag + b * F * dim : NULL;
+    for (int64_t c = 0; c < dim; ++c) {
+      R[b * W + c] = z[c];
+      rmag[b * W + c] = zm ? zm[c] : fabs(z[c]);
+    }
+    for (int64_t i = 1; i < F; ++i)
+      for (int64_t j = 0; j < i; ++j) {
+        double s = 0.0, a = 0.0;
+        for (int64_t c = 0; c < dim; ++c) {
+          s += z[i * dim + c] * z[j * dim + c];
+          double mi = zm ? zm[i * dim + c] : fabs(z[i * dim + c]);
+          double mj = zm ? zm[j * dim + c] : fabs(z[j * dim + c]);
+          a += mi * mj;
+        }
+        R[b * W + dim + i * (i - 1) / 2 + j] = s;
+        rmag[b * W + dim + i * (i - 1) / 2 + j] = a;
+      }
+  }
+}
+
+/* ------------------------------------------------------------------ a7: its gradient */
+/* Chain rule of the interaction above: with dP_ij the upstream gradient of pair (i, j),
+ * dZ_i = sum over j != i of dP_(max(i,j), min(i,j)) * z_j, and the upstream gradient of
+ * the dense passthrough adds to dZ_0.  dR: [batch][dim + P]; dZ, dmag: [batch][F][dim]. */
+void orc_interaction_bwd(const double* Z, const double* zmag, const double* dR,
+                         int64_t batch, int32_t F, int32_t dim, double* dZ, double* dmag) {
+  int64_t P = (int64_t)F * (F - 1) / 2, W = dim + P;
+#pragma omp parallel for schedule(static)
+  for (int64_t b = 0; b < batch; ++b) {
+    const double* z = Z + b * F * dim;
+    const double* zm = zmag ? zmag + b * F * dim : NULL;
+    const double* g = dR + b * W;
+    for (int64_t i = 0; i < F; ++i)
+      for (int64_t c = 0; c < dim; ++c) {
+        double s = 0.0, a = 0.0;
+        for (int64_t j = 0; j < F; ++j) {
+          if (j == i) continue;
+          int64_t hi = i > j ? i : j, lo = i > j ? j : i;
+          double gp = g[dim + hi * (hi - 1) / 2 + lo];
+          s += gp * z[j * dim + c];
+          a += fabs(gp) * (zm ? zm[j * dim + c] : fabs(z[j * dim + c]));
+        }
+        if (i == 0) {
+          s += g[c];
+          a += fabs(g[c]);
+        }
+        dZ[(b * F + i) * dim + c] = s;
+        dmag[(b * F + i) * dim + c] = a;
+      }
+  }
+}
+
+/* ------------------------------------------------------------------ a8: row gradients */
+/* Chain rule of sum pooling: every occurrence in bag (t, b) receives dY[b][t]; the rows'
+ * gradients are those summed per distinct row, in the order of uniq ([TN] "Synchronous
+ * Architecture": only rows present in the batch get a gradient).  No 1/B scaling.
+ * dY, dymag: [batch][num_tables][dim]; inverse from orc_unique; g, gmag: [U][dim]. */
+void orc_embbag_bwd(const double* dY, const double* dymag, const int64_t* offsets,
+                    int64_t batch, int32_t num_tables, int32_t dim, const int32_t* inverse,
+                    int64_t U, double* g, double* gmag) {
+  memset(g, 0, (size_t)U * dim * sizeof(double));
+  memset(gmag, 0, (size_t)U * dim * sizeof(double));
+  for (int64_t t = 0; t < num_tables; ++t)
+    for (int64_t b = 0; b < batch; ++b) {
+      int64_t s = t * batch + b;
+      const double* y = dY + (b * num_tables + t) * dim;
+      const double* ym = dymag ? dymag + (b * num_tables + t) * dim : NULL;
+      for (int64_t i = offsets[s]; i < offsets[s + 1]; ++i) {
+        int64_t u = inverse[i];
+        for (int64_t c = 0; c < dim; ++c) {
+          g[u * dim + c] += y[c];
+          gmag[u * dim + c] += ym ? ym[c] : fabs(y[c]);
+        }
+      }
+    }
+}
+
+/* ------------------------------------------------------------------ a9: sparse SGD */
+/* W[uniq[u]] <- W[uniq[u]] - lr * g[u] in double, rounded once to the storage type
+ * (binary32, or bfloat16 nearest-even).  Rows not in uniq are untouched by definition.
+ * new_rows, nmag: [U][dim] (nmag = |W| + lr * gmag). */
+void orc_sparse_sgd(const float* data, uint64_t seed, const int64_t* row_base,
+                    int32_t num_tables, int32_t dim, int32_t bf16, const int64_t* uniq,
+                    int64_t U, const double* g, const double* gmag, float lr,
+                    double* new_rows, double* nmag) {
+  orc_table tb = {data, seed, row_base, num_tables, dim, bf16};
+  double l = (double)lr;
+#pragma omp parallel for schedule(static)
+  for (int64_t u = 0; u < U; ++u)
+    for (int64_t c = 0; c < dim; ++c) {
+      double w = tval(&tb, uniq[u], c);
+      double x = w - l * g[u * dim + c];
+      new_rows[u * dim + c] = bf16 ? orc_round_bf16(x) : orc_round_f32(x);
+      nmag[u * dim + c] = fabs(w) + l * gmag[u * dim + c];
+    }
+}

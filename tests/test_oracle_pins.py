@@ -1,0 +1,355 @@
+"""Pins of the CPU oracle against facts that do not come from the oracle itself.
+
+Each test checks the oracle against brute force on tiny inputs, a library routine
+(numpy.unique, numpy.einsum, scipy.sparse SpMM, torch's bfloat16 cast), a closed form
+(the squared-norm identity of the DHEN notes, Solution 2), or an invariant, so that a
+dropped term, a wrong sign, a wrong index or a transposed operand in the oracle fails one
+of them.  No GPU is used.
+"""
+import itertools
+import math
+import os
+
+import numpy as np
+import pytest
+import scipy.sparse as sp
+import torch
+
+from oracle import oracle as orc
+from sparse_embedding_lookup_amd import workloads
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _golden_lines(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return [ln.split() for ln in f if ln.strip() and not ln.startswith("#")]
+
+
+# ----------------------------------------------------------------------------- table fill
+def test_splitmix64_known_answers():
+    want = [int(x[0], 16) for x in _golden_lines("splitmix64_seed0.txt")]
+    assert orc.splitmix64_stream(0, 3) == want
+
+
+def test_round_bf16_matches_torch_and_brute_force():
+    rng = np.random.default_rng(1)
+    xs = np.concatenate([rng.standard_normal(4000).astype(np.float32),
+                         (rng.standard_normal(1000) * 1e-3).astype(np.float32),
+                         np.array([1.0, -1.0, 0.0, 1 + 2 ** -8, 1 + 3 * 2 ** -8,
+                                   1 + 2 ** -9, 3.0e-39], dtype=np.float32)])
+    ref = torch.from_numpy(xs).to(torch.bfloat16).to(torch.float32).numpy()
+    got = np.array([orc.round_bf16(float(x)) for x in xs])
+    np.testing.assert_array_equal(got, ref.astype(np.float64))
+    # brute force on a few: nearest of all bf16 values with the same exponent, ties to even
+    for x in xs[:50]:
+        x = float(x)
+        if x == 0.0:
+            continue
+        e = math.frexp(x)[1]
+        q = 2.0 ** (e - 8)
+        lo = math.floor(x / q) * q
+        hi = lo + q
+        if x - lo < hi - x:
+            want = lo
+        elif hi - x < x - lo:
+            want = hi
+        else:
+            want = lo if int(round(lo / q)) % 2 == 0 else hi
+        assert orc.round_bf16(x) == want
+
+
+def test_table_value_definition():
+    seed, dim = 12345, 8
+    for rows_t, bf16 in [(1000, False), (4_000_000, True), (20_000_000, False)]:
+        a = np.float32(1.0 / math.sqrt(rows_t))
+        for r in [0, 1, 7, rows_t - 1]:
+            for c in [0, 3, dim - 1]:
+                st = seed ^ (r * dim + c)
+                v = orc.splitmix64_stream(st, 1)[0]
+                u = (v >> 40) / float(1 << 24)
+                x = np.float32(np.float32(2.0 * u - 1.0) * a)
+                want = orc.round_bf16(float(x)) if bf16 else float(x)
+                got = orc.table_value(seed, r, c, dim, rows_t, bf16)
+                assert got == want
+                assert -a <= got <= a
+
+
+def test_table_value_distribution():
+    tab = orc.Table([50_000], 16, "f32", 7)
+    vals = orc.table_rows(tab, np.arange(2000))
+    a = 1.0 / math.sqrt(50_000)
+    assert np.all(np.abs(vals) <= a)
+    # U(-a, a): mean 0, variance a^2/3
+    assert abs(vals.mean()) < 0.02 * a
+    assert abs(vals.var() / (a * a / 3.0) - 1.0) < 0.02
+
+
+# ----------------------------------------------------------------------------- keys
+def test_form_keys_brute_force():
+    rng = np.random.default_rng(3)
+    T, B = 3, 5
+    lengths = rng.integers(0, 4, size=(T, B))
+    off = np.zeros(T * B + 1, dtype=np.int64)
+    off[1:] = np.cumsum(lengths.reshape(-1))
+    ids = rng.integers(-10**12, 10**12, size=int(off[-1]))
+    rb = np.array([0, 10, 30, 60], dtype=np.int64)
+    for m in [0, 7, 20_000_000]:
+        got = orc.form_keys(ids, off, T, B, rb, m)
+        want = []
+        for t in range(T):
+            for b in range(B):
+                s = t * B + b
+                for i in range(off[s], off[s + 1]):
+                    v = int(ids[i]) % m if m else int(ids[i])  # Python % is floor mod
+                    want.append(int(rb[t]) + v)
+        assert got.tolist() == want
+
+
+# ----------------------------------------------------------------------------- unique
+def _check_unique(keys):
+    uniq, inv, perm, seg = orc.unique(keys)
+    n = keys.size
+    # library routine
+    u2, inv2, cnt2 = np.unique(keys, return_inverse=True, return_counts=True)
+    np.testing.assert_array_equal(uniq, u2)
+    np.testing.assert_array_equal(inv, inv2.reshape(-1))
+    np.testing.assert_array_equal(np.diff(seg), cnt2)
+    np.testing.assert_array_equal(perm, np.argsort(keys, kind="stable"))
+    # invariants
+    assert seg[0] == 0 and seg[-1] == n
+    assert np.all(np.diff(uniq) > 0)
+    np.testing.assert_array_equal(uniq[inv], keys)
+    assert sorted(perm.tolist()) == list(range(n))
+    return uniq, inv, perm, seg
+
+
+def test_unique_brute_force_small():
+    rng = np.random.default_rng(4)
+    for n in [1, 2, 17, 300]:
+        keys = rng.integers(-5, 6, size=n)
+        uniq, inv, perm, seg = _check_unique(keys)
+        # O(n^2) brute force: rank of a key = number of distinct smaller keys
+        distinct = []
+        for k in keys.tolist():
+            if k not in distinct:
+                distinct.append(k)
+        for i, k in enumerate(keys.tolist()):
+            assert inv[i] == sum(1 for d in distinct if d < k)
+        # stable: equal keys keep occurrence order
+        for u in range(uniq.size):
+            run = perm[seg[u]:seg[u + 1]]
+            assert np.all(np.diff(run) > 0)
+
+
+def test_unique_edge_cases():
+    uniq, inv, perm, seg = orc.unique(np.zeros(0, dtype=np.int64))
+    assert uniq.size == 0 and seg.tolist() == [0]
+    _check_unique(np.array([42], dtype=np.int64))
+    _check_unique(np.full(1000, -7, dtype=np.int64))                    # all equal
+    _check_unique(np.random.default_rng(5).permutation(5000).astype(np.int64))  # distinct
+    _check_unique(np.array([2**62, -2**62, 0, -1, 2**63 - 1, -2**63], dtype=np.int64))
+
+
+def test_unique_zipf_workload():
+    w = workloads.small(batch=64, rows=5000)
+    keys = orc.form_keys(w.indices, w.offsets, w.num_tables, w.batch, w.row_base)
+    _check_unique(keys)
+
+
+# ----------------------------------------------------------------------------- pooling
+def _csr(ids, off, T, B, rows):
+    """Per-table CSR matrices [B, rows_t] with one nonzero per occurrence."""
+    mats = []
+    for t in range(T):
+        lo, hi = off[t * B], off[(t + 1) * B]
+        indptr = off[t * B:(t + 1) * B + 1] - lo
+        data = np.ones(hi - lo)
+        mats.append(sp.csr_matrix((data, ids[lo:hi], indptr), shape=(B, rows[t])))
+    return mats
+
+
+def test_embbag_fwd_matches_scipy_spmm():
+    w = workloads.small(batch=32, rows=3000)
+    tab = orc.Table(w.rows, w.dim, w.dtype, w.table_seed)
+    W = orc.full_table(tab).astype(np.float64)
+    out, mag = orc.embbag_fwd(tab, w.indices, w.offsets, w.batch)
+    mats = _csr(w.indices, w.offsets, w.num_tables, w.batch, w.rows)
+    for t, M in enumerate(mats):
+        Wt = W[w.row_base[t]:w.row_base[t + 1]]
+        np.testing.assert_allclose(out[:, t, :], M @ Wt, rtol=0, atol=1e-12)
+        np.testing.assert_allclose(mag[:, t, :], M @ np.abs(Wt), rtol=0, atol=1e-12)
+
+
+def test_embbag_fwd_ones_rows_count_lengths_and_single_is_copy():
+    rows, dim, T, B = [10, 20], 4, 2, 6
+    data = np.ones((30, dim), dtype=np.float32)
+    tab = orc.Table(rows, dim, "f32", 0, data=data)
+    lengths = np.array([[0, 1, 2, 3, 4, 5], [5, 4, 0, 2, 1, 1]])
+    off = np.zeros(T * B + 1, dtype=np.int64)
+    off[1:] = np.cumsum(lengths.reshape(-1))
+    ids = np.concatenate([np.random.default_rng(0).integers(0, rows[t], int(lengths[t].sum()))
+                          for t in range(T)])
+    out, _ = orc.embbag_fwd(tab, ids, off, B)
+    np.testing.assert_array_equal(out[:, :, 0], lengths.T.astype(np.float64))
+    # bag of one = exact copy of the row (fill regenerated by the counter-based definition)
+    tab2 = orc.Table(rows, dim, "bf16", 99)
+    out2, _ = orc.embbag_fwd(tab2, ids, off, B)
+    W2 = orc.full_table(tab2)
+    t, b = 0, 1
+    k = off[t * B + b]
+    np.testing.assert_array_equal(out2[b, t], W2[tab2.row_base[t] + ids[k]].astype(np.float64))
+    assert np.all(out2[0, 0] == 0) and np.all(out2[2, 1] == 0)   # empty bags
+
+
+def test_gather_rows_is_copy():
+    tab = orc.Table([100, 50], 8, "bf16", 5)
+    W = orc.full_table(tab)
+    rows = np.array([149, 0, 77, 100])
+    np.testing.assert_array_equal(orc.gather_rows(tab, rows), W[rows].astype(np.float64))
+
+
+# ----------------------------------------------------------------------------- interaction
+def test_pair_counts_golden():
+    for F, P in _golden_lines("pair_counts.txt"):
+        F, P = int(F), int(P)
+        Z = np.random.default_rng(F).standard_normal((2, F, 4))
+        R, _ = orc.interaction_fwd(Z)
+        assert R.shape == (2, 4 + P)
+        assert P == math.comb(F, 2)
+
+
+def test_interaction_fwd_einsum_and_brute_force():
+    rng = np.random.default_rng(6)
+    B, F, d = 5, 7, 12
+    Z = rng.standard_normal((B, F, d))
+    R, Rm = orc.interaction_fwd(Z)
+    G = np.einsum("bfd,bgd->bfg", Z, Z)
+    li, lj = np.tril_indices(F, -1)           # row-major strict lower triangle: i > j
+    np.testing.assert_allclose(R[:, d:], G[:, li, lj], rtol=1e-13, atol=1e-13)
+    np.testing.assert_array_equal(R[:, :d], Z[:, 0, :])           # dense passthrough
+    # brute force with explicit pair index i(i-1)/2 + j
+    for b in range(B):
+        for i in range(1, F):
+            for j in range(i):
+                s = sum(Z[b, i, k] * Z[b, j, k] for k in range(d))
+                assert abs(R[b, d + i * (i - 1) // 2 + j] - s) < 1e-12
+                # symmetry: <z_j, z_i> is the same number
+                s2 = sum(Z[b, j, k] * Z[b, i, k] for k in range(d))
+                assert s == s2
+    Gm = np.einsum("bfd,bgd->bfg", np.abs(Z), np.abs(Z))
+    np.testing.assert_allclose(Rm[:, d:], Gm[:, li, lj], rtol=1e-13)
+
+
+def test_interaction_fm_identity():
+    """DHEN notes, Solution 2: sum over i<j of <v_i, v_j> = 1/2 (||sum v||^2 - sum ||v||^2)."""
+    rng = np.random.default_rng(7)
+    for F, d in [(5, 16), (9, 64), (27, 128)]:
+        Z = rng.standard_normal((3, F, d))
+        R, _ = orc.interaction_fwd(Z)
+        lhs = R[:, d:].sum(axis=1)
+        s = Z.sum(axis=1)
+        rhs = 0.5 * ((s * s).sum(axis=1) - (Z * Z).sum(axis=(1, 2)))
+        np.testing.assert_allclose(lhs, rhs, rtol=1e-10, atol=1e-10)
+
+
+def test_interaction_bwd_closed_form_fm_gradient():
+    """With every pair gradient 1 and no dense gradient, dZ_i = sum_j z_j - z_i (the
+    gradient of the squared-norm identity)."""
+    rng = np.random.default_rng(8)
+    B, F, d = 4, 6, 8
+    Z = rng.standard_normal((B, F, d))
+    dR = np.zeros((B, d + F * (F - 1) // 2))
+    dR[:, d:] = 1.0
+    dZ, _ = orc.interaction_bwd(Z, dR)
+    want = Z.sum(axis=1, keepdims=True) - Z
+    np.testing.assert_allclose(dZ, want, rtol=1e-12, atol=1e-12)
+
+
+def test_interaction_bwd_adjoint_and_finite_differences():
+    rng = np.random.default_rng(9)
+    B, F, d = 3, 5, 6
+    P = F * (F - 1) // 2
+    Z = rng.standard_normal((B, F, d))
+    dR = rng.standard_normal((B, d + P))
+    dZ, _ = orc.interaction_bwd(Z, dR)
+    # the forward is quadratic in Z, so central differences give J.dZ up to rounding
+    V = rng.standard_normal((B, F, d))
+    eps = 1e-3
+    Rp, _ = orc.interaction_fwd(Z + eps * V)
+    Rn, _ = orc.interaction_fwd(Z - eps * V)
+    JV = (Rp - Rn) / (2 * eps)
+    lhs = float((dR * JV).sum())
+    rhs = float((dZ * V).sum())
+    assert abs(lhs - rhs) < 1e-8 * (1 + abs(lhs))
+    # element-wise finite differences
+    for (b, i, k) in [(0, 0, 0), (1, 3, 2), (2, 4, 5)]:
+        E = np.zeros_like(Z)
+        E[b, i, k] = 1.0
+        Rp, _ = orc.interaction_fwd(Z + eps * E)
+        Rn, _ = orc.interaction_fwd(Z - eps * E)
+        fd = float((dR * (Rp - Rn)).sum() / (2 * eps))
+        assert abs(fd - dZ[b, i, k]) < 1e-8
+
+
+# ----------------------------------------------------------------------------- backward
+def _bag_setup(seed=10, T=3, B=16, rows=(50, 80, 30), d=4):
+    rng = np.random.default_rng(seed)
+    lengths = rng.integers(0, 6, size=(T, B))
+    off = np.zeros(T * B + 1, dtype=np.int64)
+    off[1:] = np.cumsum(lengths.reshape(-1))
+    ids = np.concatenate([rng.integers(0, rows[t], int(lengths[t].sum())) for t in range(T)])
+    rb = np.zeros(T + 1, dtype=np.int64)
+    rb[1:] = np.cumsum(rows)
+    keys = orc.form_keys(ids, off, T, B, rb)
+    dY = rng.standard_normal((B, T, d))
+    return lengths, off, ids, rb, keys, dY
+
+
+def test_embbag_bwd_matches_scipy_transpose_and_conserves():
+    T, B, rows, d = 3, 16, (50, 80, 30), 4
+    lengths, off, ids, rb, keys, dY = _bag_setup(T=T, B=B, rows=rows, d=d)
+    uniq, inv, perm, seg = orc.unique(keys)
+    g, gm = orc.embbag_bwd(dY, off, B, T, inv, uniq.size)
+    # CSR^T @ dY per table, then pick the touched rows
+    full = np.zeros((int(rb[-1]), d))
+    for t, M in enumerate(_csr(ids, off, T, B, list(rows))):
+        full[rb[t]:rb[t + 1]] = M.T @ dY[:, t, :]
+    np.testing.assert_allclose(g, full[uniq], rtol=1e-13, atol=1e-13)
+    # conservation: per table, sum of row gradients = sum_b len(b) * dY[b, t]
+    for t in range(T):
+        mask = (uniq >= rb[t]) & (uniq < rb[t + 1])
+        lhs = g[mask].sum(axis=0)
+        rhs = (lengths[t][:, None] * dY[:, t, :]).sum(axis=0)
+        np.testing.assert_allclose(lhs, rhs, rtol=1e-12, atol=1e-12)
+    # dY = 1 gives the occurrence counts exactly
+    g1, _ = orc.embbag_bwd(np.ones_like(dY), off, B, T, inv, uniq.size)
+    np.testing.assert_array_equal(g1[:, 0], np.diff(seg).astype(np.float64))
+
+
+def test_sparse_sgd_closed_form():
+    tab = orc.Table([40, 60], 8, "f32", 11)
+    W = orc.full_table(tab).astype(np.float64)
+    uniq = np.array([3, 39, 40, 99])
+    rng = np.random.default_rng(12)
+    g = rng.standard_normal((4, 8))
+    lr = 0.01
+    new, nm = orc.sparse_sgd(tab, uniq, g, np.abs(g), lr)
+    want = (W[uniq] - np.float64(np.float32(lr)) * g).astype(np.float32).astype(np.float64)
+    np.testing.assert_array_equal(new, want)
+    same, _ = orc.sparse_sgd(tab, uniq, g, np.abs(g), 0.0)
+    np.testing.assert_array_equal(same, W[uniq])                  # lr = 0: unchanged
+    tabb = orc.Table([40, 60], 8, "bf16", 11)
+    Wb = orc.full_table(tabb).astype(np.float64)
+    newb, _ = orc.sparse_sgd(tabb, uniq, g, np.abs(g), lr)
+    x = torch.from_numpy(Wb[uniq] - np.float64(np.float32(lr)) * g)
+    # torch casts fp64 -> bf16 directly with nearest-even
+    np.testing.assert_array_equal(newb, x.to(torch.bfloat16).to(torch.float64).numpy())
+
+
+def test_magnitudes_bound_values():
+    w = workloads.tiny()
+    tab = orc.Table(w.rows, w.dim, w.dtype, w.table_seed)
+    out, mag = orc.embbag_fwd(tab, w.indices, w.offsets, w.batch)
+    assert np.all(mag >= np.abs(out))
+    np.testing.assert_array_equal(mag, np.abs(out))      # bags of one: M = |row|
