@@ -1,0 +1,202 @@
+/*
+ * ctr.h -- C ABI of libctr, the MI355X (gfx950) sparse front end of a CTR ranking model.
+ *
+ * The path: batch ID deduplication (sort, unique, inverse map), a fetch of the batch's
+ * rows into a batch-sized matrix, sum-pooled embedding bags, the pairwise-dot interaction
+ * of the pooled vectors with the dense vector, and backward: the interaction gradient, the
+ * per-row gradient sum and a sparse SGD update of the touched rows only.
+ *
+ * Sources (web pages, by title and section):
+ *   [TN]   "How TensorNet Supercharges Sparse Feature Training on TensorFlow",
+ *          "Core Optimizations" (collect the batch's IDs, sort them, give each a contiguous
+ *          index, fetch rows into a matrix sized to the batch) and "Synchronous
+ *          Architecture" (only the features present in the batch are synchronized).
+ *   [DHEN] "DHEN" notes (calwoo.github.io), 2.1 "Feature Processing Layer" (a trainable
+ *          d-dim vector per categorical term, dense features to one d-dim vector, all
+ *          slots concatenated) and 3.1 "AdvancedDLRM" with Solution 2 (all pairwise inner
+ *          products, C(m,2) of them, concatenated with the dense features).
+ *   [DLRM] "Meta DLRM" (upskillscore.com), 02 "Arquitetura": the interaction is the dot
+ *          product between all pairs of embedding vectors and the processed dense features.
+ *
+ * Conventions shared by every entry point
+ *   - Every pointer argument is DEVICE memory unless marked "host".  The caller owns all
+ *     buffers; the library never allocates, frees or synchronizes.  Each call only enqueues
+ *     work on `stream` (a hipStream_t; NULL is the null stream) and returns.
+ *   - Arguments are checked on the host before any launch; a bad argument returns a status
+ *     without touching the device: CTR_ERR_INVALID_ARGUMENT (null required pointer, negative
+ *     or too large size, F < 2, stride smaller than the row), CTR_ERR_UNSUPPORTED (pointer
+ *     not 16-byte aligned, dim not a multiple of the 16-byte vector, dim or F beyond the
+ *     kernel's limits), CTR_ERR_WORKSPACE_TOO_SMALL.  A launch failure returns CTR_ERR_HIP.
+ *     ctr_last_error() gives a thread-local text of the last failure.
+ *   - Sizes that index elements must be < 2^31 (n, nnz, number of bags).
+ *   - Data preconditions (0 <= index < rows of its table, offsets non-decreasing from 0 to
+ *     nnz) are not checked on the hot path; ctr_validate_csr checks them.  Kernels clamp
+ *     every device-side index so that bad data gives bad numbers (NaN rows for out-of-range
+ *     lookups), never an out-of-bounds access.
+ *   - Device counts (num_unique) stay on the device; consumers read them there and launch
+ *     for the capacity.
+ *   - Calls that take `workspace` use a two-call query: with workspace == NULL the call only
+ *     stores the required byte count in *workspace_bytes and returns CTR_OK.
+ *   - Tables: all tables of a model live in ONE row-major allocation [total_rows, dim] of
+ *     fp32 or bf16 (16-byte aligned); table t owns rows [row_base[t], row_base[t+1]).
+ *     Bags are CSR, table-major: bag (t, b) spans indices[offsets[t*batch+b] ..
+ *     offsets[t*batch+b+1]).
+ */
+#ifndef CTR_H
+#define CTR_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  CTR_OK = 0,
+  CTR_ERR_INVALID_ARGUMENT = 1,
+  CTR_ERR_UNSUPPORTED = 2,
+  CTR_ERR_WORKSPACE_TOO_SMALL = 3,
+  CTR_ERR_HIP = 4
+} ctr_status_t;
+
+typedef enum { CTR_F32 = 0, CTR_BF16 = 1 } ctr_dtype_t;
+typedef enum { CTR_I32 = 0, CTR_I64 = 1 } ctr_index_t;
+
+/* Library version (major*10000 + minor*100 + patch). */
+int32_t ctr_version(void);
+
+/* Text of a status code (static storage). */
+const char* ctr_status_string(int32_t status);
+
+/* Thread-local text of the last failure in this thread ("" if none). */
+const char* ctr_last_error(void);
+
+/*
+ * ctr_unique_ids -- [TN] "Core Optimizations": collect the batch's IDs, sort them and give
+ * each distinct ID a contiguous index (the virtual sparse feature).
+ *
+ * Key of occurrence i (a1):
+ *   id   = ids[i] (int32 or int64 per id_type)
+ *   r    = key_modulus > 0 ? floor_mod(id, key_modulus) : id
+ *   key  = (row_base != NULL ? row_base[t] : 0) + r, where bag (t, b) holds occurrence i
+ *          (offsets/batch/num_tables give the bags; offsets is required with row_base).
+ * Outputs (a2), with U = number of distinct keys:
+ *   uniq[u]          distinct keys ascending (signed compare), u < U          int64 [n]
+ *   inverse[i]       u such that uniq[u] == key(i)                            int32 [n]
+ *   num_unique[0]    U                                                        int32 (device)
+ *   perm[p]          occurrence at sorted position p, ties in occurrence order int32 [n]
+ *                    (nullable)
+ *   seg_offsets[u]   first sorted position of uniq[u]; seg_offsets[U] = n      int32 [n+1]
+ *                    (nullable)
+ * Key range: with row_base the keys must lie in [0, total_rows); with only a modulus in
+ * [0, key_modulus); otherwise any int64.  The sort covers only the live key bits.
+ * n == 0 is legal: U = 0, seg_offsets[0] = 0.
+ */
+int32_t ctr_unique_ids(const void* ids, int32_t id_type, int64_t n,
+                       const int64_t* offsets, int64_t batch, int32_t num_tables,
+                       const int64_t* row_base, int64_t total_rows, int64_t key_modulus,
+                       int64_t* uniq, int32_t* inverse, int32_t* num_unique,
+                       int32_t* perm, int32_t* seg_offsets,
+                       void* workspace, size_t* workspace_bytes, void* stream);
+
+/*
+ * ctr_gather_rows -- [TN] "Core Optimizations": fetch the batch's rows into the
+ * batch-sized matrix.  out[u, :] = table[rows[u], :] widened to fp32, for
+ * u < min(num_rows[0], capacity); rows of out at or beyond that are not written.
+ * out: fp32 [capacity, dim], 16-byte aligned.
+ */
+int32_t ctr_gather_rows(const void* table, int32_t dtype, int64_t total_rows, int32_t dim,
+                        const int64_t* rows, const int32_t* num_rows, int64_t capacity,
+                        float* out, void* stream);
+
+/*
+ * ctr_embbag_fwd -- [DHEN] 2.1: one d-dim vector per sparse feature, by sum pooling.
+ * For every bag (t, b), t < num_tables, b < batch:
+ *   out[b*out_stride_b + t*out_stride_t + c] = sum over k in the bag of
+ *       table[(row_base ? row_base[t] : 0) + indices[k], c]       (fp32 accumulation)
+ * Duplicates count with multiplicity; an empty bag writes zeros.  out_stride_* are in
+ * floats and multiples of 4, so the pooled vectors can go straight into Z[b, 1 + t, :].
+ * indices: int32 or int64 [nnz]; offsets: int64 [num_tables*batch + 1].
+ */
+int32_t ctr_embbag_fwd(const void* table, int32_t dtype, int64_t total_rows, int32_t dim,
+                       const int64_t* row_base, int32_t num_tables,
+                       const void* indices, int32_t index_type, int64_t nnz,
+                       const int64_t* offsets, int64_t batch,
+                       float* out, int64_t out_stride_b, int64_t out_stride_t, void* stream);
+
+/*
+ * ctr_embbag_bwd -- chain rule of the sum pooling, reduced per distinct row ([TN]
+ * "Synchronous Architecture": only rows present in the batch receive anything).
+ *   row_grads[u, c] = sum over occurrences i with inverse[i] == u of
+ *                     grad[b(i)*grad_stride_b + t(i)*grad_stride_t + c]
+ * where bag (t(i), b(i)) holds occurrence i.  perm and inverse are ctr_unique_ids outputs
+ * for the same occurrences; the sum runs in sorted order as a fixed-shape tree over
+ * chunks (deterministic, no atomics).  row_grads: fp32 [nnz, dim]; rows u >= U untouched.
+ * Workspace: two-call query.
+ */
+int32_t ctr_embbag_bwd(const float* grad, int64_t grad_stride_b, int64_t grad_stride_t,
+                       const int64_t* offsets, int64_t batch, int32_t num_tables, int32_t dim,
+                       int64_t nnz, const int32_t* perm, const int32_t* inverse,
+                       const int32_t* num_unique, float* row_grads,
+                       void* workspace, size_t* workspace_bytes, void* stream);
+
+/*
+ * ctr_sparse_sgd -- update of the touched rows only ([TN] "Synchronous Architecture"):
+ *   table[uniq[u], :] = round(table[uniq[u], :] - lr * row_grads[u, :])
+ * for u < min(num_unique[0], capacity), computed in fp32 (one fused multiply-add) and
+ * stored as fp32 or rounded to bf16 nearest-even.  Keys must be distinct (ctr_unique_ids
+ * output), so no two threads touch one row; untouched rows stay bit-identical.
+ */
+int32_t ctr_sparse_sgd(void* table, int32_t dtype, int64_t total_rows, int32_t dim,
+                       const int64_t* uniq, const int32_t* num_unique, int64_t capacity,
+                       const float* row_grads, float lr, void* stream);
+
+/*
+ * ctr_dot_interaction_fwd -- [DLRM] 02, [DHEN] 3.1 and Solution 2.  Z: fp32 [batch, F, dim]
+ * with Z[b, 0, :] the dense vector and Z[b, 1 + t, :] the pooled vectors.
+ *   R[b*r_stride + c]                      = Z[b, 0, c]            c < dim
+ *   R[b*r_stride + dim + i*(i-1)/2 + j]    = <Z[b, i, :], Z[b, j, :]>   F > i > j >= 0
+ * compute = CTR_F32: fp32 arithmetic.  compute = CTR_BF16: operands rounded to bf16
+ * (nearest-even) on matrix cores, fp32 accumulation (dim a multiple of 16, F <= 128).
+ */
+int32_t ctr_dot_interaction_fwd(const float* Z, int64_t batch, int32_t num_vectors, int32_t dim,
+                                int32_t compute, float* R, int64_t r_stride, void* stream);
+
+/*
+ * ctr_dot_interaction_bwd -- chain rule of the above.  With dP_ij = dR[b*dr_stride + dim +
+ * i*(i-1)/2 + j] for i > j:
+ *   dZ[b, i, :] = sum over j != i of dP_(max(i,j), min(i,j)) * Z[b, j, :]
+ *                 + (i == 0 ? dR[b*dr_stride + 0 .. dim) : 0)
+ * dZ: fp32 [batch, F, dim].  compute as in the forward (bf16 rounds dP and Z).
+ */
+int32_t ctr_dot_interaction_bwd(const float* Z, const float* dR, int64_t dr_stride,
+                                int64_t batch, int32_t num_vectors, int32_t dim,
+                                int32_t compute, float* dZ, void* stream);
+
+/*
+ * ctr_init_table_hash -- fills a table with the counter-based values used by the seeded
+ * workloads (input preparation, not part of the method): element (r, c) of table t is
+ * x = fp32(2u - 1) * fp32(1/sqrt(rows_t)) with u = (splitmix64 output from state
+ * seed ^ (r*dim + c)) >> 40, times 2^-24, stored as fp32 or bf16 nearest-even.
+ * row_base_host: host int64 [num_tables + 1].
+ */
+int32_t ctr_init_table_hash(void* table, int32_t dtype, int32_t dim,
+                            const int64_t* row_base_host, int32_t num_tables, uint64_t seed,
+                            void* stream);
+
+/*
+ * ctr_validate_csr -- debug check of the data preconditions: offsets[0] == 0, offsets
+ * non-decreasing, offsets[last] == nnz, and 0 <= indices[k] < rows of the bag's table
+ * (row_base given: rows_t = row_base[t+1] - row_base[t]; else total_rows).  Adds the number
+ * of violations to bad_count[0] (int32, device; the caller zeroes it).
+ */
+int32_t ctr_validate_csr(const void* indices, int32_t index_type, int64_t nnz,
+                         const int64_t* offsets, int64_t batch, int32_t num_tables,
+                         const int64_t* row_base, int64_t total_rows, int32_t* bad_count,
+                         void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* CTR_H */

@@ -1,0 +1,302 @@
+// capi.cpp -- the C ABI of libctr: host-side argument checks, workspace sizing, launches.
+// Every check runs before the first HIP call, so a bad argument never touches the device.
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <cmath>
+
+#include "../../include/ctr.h"
+#include "ctr_internal.h"
+
+namespace {
+
+thread_local char g_msg[512] = "";
+
+int32_t fail(int32_t code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_msg, sizeof(g_msg), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int32_t hip_status(hipError_t e, const char* where) {
+  if (e == hipSuccess) return CTR_OK;
+  return fail(CTR_ERR_HIP, "%s: %s", where, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+constexpr int64_t kMaxElems = 2147483647;  // int32 positions and indices
+
+int bitlen(uint64_t x) {
+  int b = 0;
+  while (x) {
+    ++b;
+    x >>= 1;
+  }
+  return b;
+}
+
+int32_t check_table(const void* table, int32_t dtype, int64_t total_rows, int32_t dim) {
+  if (!table) return fail(CTR_ERR_INVALID_ARGUMENT, "table is NULL");
+  if (dtype != CTR_F32 && dtype != CTR_BF16)
+    return fail(CTR_ERR_INVALID_ARGUMENT, "dtype %d is not CTR_F32 or CTR_BF16", dtype);
+  if (total_rows < 0) return fail(CTR_ERR_INVALID_ARGUMENT, "total_rows < 0");
+  if (dim <= 0) return fail(CTR_ERR_INVALID_ARGUMENT, "dim must be positive");
+  const int e = dtype == CTR_BF16 ? 8 : 4;
+  if (dim % e != 0)
+    return fail(CTR_ERR_UNSUPPORTED, "dim %d is not a multiple of the 16-byte vector (%d)", dim, e);
+  if (dim / e > 256) return fail(CTR_ERR_UNSUPPORTED, "dim %d above the 4 KiB row limit", dim);
+  if (!aligned16(table)) return fail(CTR_ERR_UNSUPPORTED, "table is not 16-byte aligned");
+  return CTR_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t ctr_version(void) { return 100; }
+
+const char* ctr_status_string(int32_t status) {
+  switch (status) {
+    case CTR_OK: return "CTR_OK";
+    case CTR_ERR_INVALID_ARGUMENT: return "CTR_ERR_INVALID_ARGUMENT";
+    case CTR_ERR_UNSUPPORTED: return "CTR_ERR_UNSUPPORTED";
+    case CTR_ERR_WORKSPACE_TOO_SMALL: return "CTR_ERR_WORKSPACE_TOO_SMALL";
+    case CTR_ERR_HIP: return "CTR_ERR_HIP";
+    default: return "CTR_ERR_UNKNOWN";
+  }
+}
+
+const char* ctr_last_error(void) { return g_msg; }
+
+int32_t ctr_unique_ids(const void* ids, int32_t id_type, int64_t n, const int64_t* offsets,
+                       int64_t batch, int32_t num_tables, const int64_t* row_base,
+                       int64_t total_rows, int64_t key_modulus, int64_t* uniq,
+                       int32_t* inverse, int32_t* num_unique, int32_t* perm,
+                       int32_t* seg_offsets, void* workspace, size_t* workspace_bytes,
+                       void* stream) {
+  g_msg[0] = 0;
+  if (!workspace_bytes) return fail(CTR_ERR_INVALID_ARGUMENT, "workspace_bytes is NULL");
+  if (n < 0 || n > kMaxElems) return fail(CTR_ERR_INVALID_ARGUMENT, "n=%lld out of [0, 2^31)", (long long)n);
+  if (id_type != CTR_I32 && id_type != CTR_I64)
+    return fail(CTR_ERR_INVALID_ARGUMENT, "id_type %d is not CTR_I32 or CTR_I64", id_type);
+  if (key_modulus < 0) return fail(CTR_ERR_INVALID_ARGUMENT, "key_modulus < 0");
+  if (row_base) {
+    if (!offsets) return fail(CTR_ERR_INVALID_ARGUMENT, "row_base needs offsets");
+    if (num_tables < 1 || num_tables > 4096)
+      return fail(CTR_ERR_UNSUPPORTED, "num_tables %d out of [1, 4096]", num_tables);
+    if (batch < 0 || (int64_t)num_tables * batch > kMaxElems)
+      return fail(CTR_ERR_INVALID_ARGUMENT, "bad batch %lld", (long long)batch);
+    if (total_rows < 1) return fail(CTR_ERR_INVALID_ARGUMENT, "total_rows must be >= 1");
+  }
+  const size_t need = ctr::unique_workspace_bytes(n, perm != nullptr);
+  if (!workspace) {
+    *workspace_bytes = need;
+    return CTR_OK;
+  }
+  if (*workspace_bytes < need)
+    return fail(CTR_ERR_WORKSPACE_TOO_SMALL, "workspace %zu < %zu bytes", *workspace_bytes, need);
+  if (!num_unique) return fail(CTR_ERR_INVALID_ARGUMENT, "num_unique is NULL");
+  if (n > 0 && (!ids || !uniq || !inverse))
+    return fail(CTR_ERR_INVALID_ARGUMENT, "ids, uniq and inverse are required");
+  int bits;
+  bool is_signed = false;
+  if (row_base) {
+    bits = bitlen((uint64_t)(total_rows - 1));
+  } else if (key_modulus > 0) {
+    bits = bitlen((uint64_t)(key_modulus - 1));
+  } else {
+    bits = 64;
+    is_signed = true;
+  }
+  if (bits < 1) bits = 1;
+  return hip_status(ctr::launch_unique(ids, id_type == CTR_I64, n, offsets, batch, num_tables,
+                                       row_base, key_modulus, bits, is_signed, uniq, inverse,
+                                       num_unique, perm, seg_offsets, workspace,
+                                       (hipStream_t)stream),
+                    "ctr_unique_ids");
+}
+
+int32_t ctr_gather_rows(const void* table, int32_t dtype, int64_t total_rows, int32_t dim,
+                        const int64_t* rows, const int32_t* num_rows, int64_t capacity,
+                        float* out, void* stream) {
+  g_msg[0] = 0;
+  int32_t st = check_table(table, dtype, total_rows, dim);
+  if (st) return st;
+  if (capacity < 0 || capacity > kMaxElems) return fail(CTR_ERR_INVALID_ARGUMENT, "bad capacity");
+  if (capacity > 0 && (!rows || !num_rows || !out))
+    return fail(CTR_ERR_INVALID_ARGUMENT, "rows, num_rows and out are required");
+  if (out && !aligned16(out)) return fail(CTR_ERR_UNSUPPORTED, "out is not 16-byte aligned");
+  return hip_status(ctr::launch_gather_rows(table, dtype == CTR_BF16, total_rows, dim, rows,
+                                            num_rows, capacity, out, (hipStream_t)stream),
+                    "ctr_gather_rows");
+}
+
+int32_t ctr_embbag_fwd(const void* table, int32_t dtype, int64_t total_rows, int32_t dim,
+                       const int64_t* row_base, int32_t num_tables, const void* indices,
+                       int32_t index_type, int64_t nnz, const int64_t* offsets, int64_t batch,
+                       float* out, int64_t out_stride_b, int64_t out_stride_t, void* stream) {
+  g_msg[0] = 0;
+  int32_t st = check_table(table, dtype, total_rows, dim);
+  if (st) return st;
+  if (index_type != CTR_I32 && index_type != CTR_I64)
+    return fail(CTR_ERR_INVALID_ARGUMENT, "index_type %d is not CTR_I32 or CTR_I64", index_type);
+  if (num_tables < 1) return fail(CTR_ERR_INVALID_ARGUMENT, "num_tables must be >= 1");
+  if (batch < 0 || (int64_t)num_tables * batch > kMaxElems)
+    return fail(CTR_ERR_INVALID_ARGUMENT, "bad batch %lld", (long long)batch);
+  if (nnz < 0 || nnz > kMaxElems) return fail(CTR_ERR_INVALID_ARGUMENT, "bad nnz");
+  if (!offsets || !out) return fail(CTR_ERR_INVALID_ARGUMENT, "offsets and out are required");
+  if (nnz > 0 && !indices) return fail(CTR_ERR_INVALID_ARGUMENT, "indices is NULL");
+  if (out_stride_b < 0 || out_stride_t < 0)
+    return fail(CTR_ERR_INVALID_ARGUMENT, "negative output stride");
+  if (num_tables > 1 && out_stride_t < dim && out_stride_b < dim)
+    return fail(CTR_ERR_INVALID_ARGUMENT, "output strides smaller than dim");
+  if (!aligned16(out) || out_stride_b % 4 || out_stride_t % 4)
+    return fail(CTR_ERR_UNSUPPORTED, "out must be 16-byte aligned with strides multiple of 4");
+  return hip_status(ctr::launch_embbag_fwd(table, dtype == CTR_BF16, total_rows, dim, row_base,
+                                           num_tables, indices, index_type == CTR_I64, nnz,
+                                           offsets, batch, out, out_stride_b, out_stride_t,
+                                           (hipStream_t)stream),
+                    "ctr_embbag_fwd");
+}
+
+int32_t ctr_embbag_bwd(const float* grad, int64_t grad_stride_b, int64_t grad_stride_t,
+                       const int64_t* offsets, int64_t batch, int32_t num_tables, int32_t dim,
+                       int64_t nnz, const int32_t* perm, const int32_t* inverse,
+                       const int32_t* num_unique, float* row_grads, void* workspace,
+                       size_t* workspace_bytes, void* stream) {
+  g_msg[0] = 0;
+  if (!workspace_bytes) return fail(CTR_ERR_INVALID_ARGUMENT, "workspace_bytes is NULL");
+  if (dim <= 0) return fail(CTR_ERR_INVALID_ARGUMENT, "dim must be positive");
+  if (dim % 4) return fail(CTR_ERR_UNSUPPORTED, "dim %d is not a multiple of 4", dim);
+  if (dim > 1024) return fail(CTR_ERR_UNSUPPORTED, "dim %d above 1024", dim);
+  if (nnz < 0 || nnz > kMaxElems) return fail(CTR_ERR_INVALID_ARGUMENT, "bad nnz");
+  if (num_tables < 1) return fail(CTR_ERR_INVALID_ARGUMENT, "num_tables must be >= 1");
+  if (batch < 0 || (int64_t)num_tables * batch > kMaxElems)
+    return fail(CTR_ERR_INVALID_ARGUMENT, "bad batch");
+  if (nnz > 0 && batch == 0)
+    return fail(CTR_ERR_INVALID_ARGUMENT, "nnz > 0 needs at least one bag");
+  const size_t need = ctr::embbag_bwd_workspace_bytes(nnz, dim);
+  if (!workspace) {
+    *workspace_bytes = need;
+    return CTR_OK;
+  }
+  if (*workspace_bytes < need)
+    return fail(CTR_ERR_WORKSPACE_TOO_SMALL, "workspace %zu < %zu bytes", *workspace_bytes, need);
+  if (!offsets || !num_unique) return fail(CTR_ERR_INVALID_ARGUMENT, "offsets and num_unique are required");
+  if (nnz > 0 && (!grad || !perm || !inverse || !row_grads))
+    return fail(CTR_ERR_INVALID_ARGUMENT, "grad, perm, inverse and row_grads are required");
+  if (grad_stride_b < 0 || grad_stride_t < 0)
+    return fail(CTR_ERR_INVALID_ARGUMENT, "negative gradient stride");
+  if ((grad && !aligned16(grad)) || (row_grads && !aligned16(row_grads)) || grad_stride_b % 4 ||
+      grad_stride_t % 4)
+    return fail(CTR_ERR_UNSUPPORTED, "grad/row_grads must be 16-byte aligned, strides multiple of 4");
+  if (!aligned16(workspace)) return fail(CTR_ERR_UNSUPPORTED, "workspace is not 16-byte aligned");
+  return hip_status(ctr::launch_embbag_bwd(grad, grad_stride_b, grad_stride_t, offsets, batch,
+                                           num_tables, dim, nnz, perm, inverse, num_unique,
+                                           row_grads, workspace, (hipStream_t)stream),
+                    "ctr_embbag_bwd");
+}
+
+int32_t ctr_sparse_sgd(void* table, int32_t dtype, int64_t total_rows, int32_t dim,
+                       const int64_t* uniq, const int32_t* num_unique, int64_t capacity,
+                       const float* row_grads, float lr, void* stream) {
+  g_msg[0] = 0;
+  int32_t st = check_table(table, dtype, total_rows, dim);
+  if (st) return st;
+  if (capacity < 0 || capacity > kMaxElems) return fail(CTR_ERR_INVALID_ARGUMENT, "bad capacity");
+  if (capacity > 0 && (!uniq || !num_unique || !row_grads))
+    return fail(CTR_ERR_INVALID_ARGUMENT, "uniq, num_unique and row_grads are required");
+  if (!std::isfinite(lr)) return fail(CTR_ERR_INVALID_ARGUMENT, "lr is not finite");
+  if (row_grads && !aligned16(row_grads))
+    return fail(CTR_ERR_UNSUPPORTED, "row_grads is not 16-byte aligned");
+  return hip_status(ctr::launch_sparse_sgd(table, dtype == CTR_BF16, total_rows, dim, uniq,
+                                           num_unique, capacity, row_grads, lr,
+                                           (hipStream_t)stream),
+                    "ctr_sparse_sgd");
+}
+
+static int32_t check_interaction(const float* Z, int64_t batch, int32_t F, int32_t dim,
+                                 int32_t compute, const float* out, int64_t stride) {
+  if (batch < 0 || batch > kMaxElems) return fail(CTR_ERR_INVALID_ARGUMENT, "bad batch");
+  if (F < 2) return fail(CTR_ERR_INVALID_ARGUMENT, "num_vectors must be >= 2 (got %d)", F);
+  if (dim <= 0) return fail(CTR_ERR_INVALID_ARGUMENT, "dim must be positive");
+  if (compute != CTR_F32 && compute != CTR_BF16)
+    return fail(CTR_ERR_INVALID_ARGUMENT, "compute %d is not CTR_F32 or CTR_BF16", compute);
+  if (batch > 0 && (!Z || !out)) return fail(CTR_ERR_INVALID_ARGUMENT, "Z and output are required");
+  const int64_t P = (int64_t)F * (F - 1) / 2;
+  if (stride < dim + P) return fail(CTR_ERR_INVALID_ARGUMENT, "stride %lld < dim + P", (long long)stride);
+  if (compute == CTR_BF16) {
+    if (!ctr::interaction_bf16_supported(F, dim))
+      return fail(CTR_ERR_UNSUPPORTED, "bf16 path needs dim in {16,32,64,128}, F <= 128");
+    if (Z && !aligned16(Z)) return fail(CTR_ERR_UNSUPPORTED, "Z is not 16-byte aligned");
+  } else if (!ctr::interaction_f32_supported(F, dim)) {
+    return fail(CTR_ERR_UNSUPPORTED, "fp32 path: one sample of F=%d, dim=%d exceeds 64 KiB of LDS", F, dim);
+  }
+  return CTR_OK;
+}
+
+int32_t ctr_dot_interaction_fwd(const float* Z, int64_t batch, int32_t num_vectors, int32_t dim,
+                                int32_t compute, float* R, int64_t r_stride, void* stream) {
+  g_msg[0] = 0;
+  int32_t st = check_interaction(Z, batch, num_vectors, dim, compute, R, r_stride);
+  if (st) return st;
+  return hip_status(ctr::launch_interaction_fwd(Z, batch, num_vectors, dim, compute == CTR_BF16,
+                                                R, r_stride, (hipStream_t)stream),
+                    "ctr_dot_interaction_fwd");
+}
+
+int32_t ctr_dot_interaction_bwd(const float* Z, const float* dR, int64_t dr_stride,
+                                int64_t batch, int32_t num_vectors, int32_t dim, int32_t compute,
+                                float* dZ, void* stream) {
+  g_msg[0] = 0;
+  int32_t st = check_interaction(Z, batch, num_vectors, dim, compute, dZ, dr_stride);
+  if (st) return st;
+  if (batch > 0 && !dR) return fail(CTR_ERR_INVALID_ARGUMENT, "dR is NULL");
+  return hip_status(ctr::launch_interaction_bwd(Z, dR, dr_stride, batch, num_vectors, dim,
+                                                compute == CTR_BF16, dZ, (hipStream_t)stream),
+                    "ctr_dot_interaction_bwd");
+}
+
+int32_t ctr_init_table_hash(void* table, int32_t dtype, int32_t dim, const int64_t* row_base_host,
+                            int32_t num_tables, uint64_t seed, void* stream) {
+  g_msg[0] = 0;
+  if (!row_base_host || num_tables < 1)
+    return fail(CTR_ERR_INVALID_ARGUMENT, "row_base_host and num_tables >= 1 are required");
+  for (int32_t t = 0; t < num_tables; ++t)
+    if (row_base_host[t + 1] < row_base_host[t] || row_base_host[0] != 0)
+      return fail(CTR_ERR_INVALID_ARGUMENT, "row_base_host must start at 0 and not decrease");
+  int32_t st = check_table(table, dtype, row_base_host[num_tables], dim);
+  if (st) return st;
+  for (int32_t t = 0; t < num_tables; ++t) {
+    const int64_t rows = row_base_host[t + 1] - row_base_host[t];
+    if (rows == 0) continue;
+    const float scale = (float)(1.0 / std::sqrt((double)rows));
+    hipError_t e = ctr::launch_init_table(table, dtype == CTR_BF16, dim, row_base_host[t], rows,
+                                          scale, seed, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_status(e, "ctr_init_table_hash");
+  }
+  return CTR_OK;
+}
+
+int32_t ctr_validate_csr(const void* indices, int32_t index_type, int64_t nnz,
+                         const int64_t* offsets, int64_t batch, int32_t num_tables,
+                         const int64_t* row_base, int64_t total_rows, int32_t* bad_count,
+                         void* stream) {
+  g_msg[0] = 0;
+  if (index_type != CTR_I32 && index_type != CTR_I64)
+    return fail(CTR_ERR_INVALID_ARGUMENT, "index_type %d is not CTR_I32 or CTR_I64", index_type);
+  if (nnz < 0 || nnz > kMaxElems || batch < 0 || num_tables < 1 ||
+      (int64_t)num_tables * batch > kMaxElems)
+    return fail(CTR_ERR_INVALID_ARGUMENT, "bad sizes");
+  if (!offsets || !bad_count || (nnz > 0 && !indices))
+    return fail(CTR_ERR_INVALID_ARGUMENT, "offsets, bad_count and indices are required");
+  return hip_status(ctr::launch_validate_csr(indices, index_type == CTR_I64, nnz, offsets, batch,
+                                             num_tables, row_base, total_rows, bad_count,
+                                             (hipStream_t)stream),
+                    "ctr_validate_csr");
+}
+
+}  // extern "C"

@@ -1,0 +1,125 @@
+// ctr_internal.h -- device helpers and kernel launchers shared by the libctr sources.
+// Written for gfx950 (CDNA4, wave64) only.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace ctr {
+
+constexpr int kWave = 64;
+
+// ----------------------------------------------------------------------------- bf16
+// bf16 is the top half of a binary32; widening is exact.
+__device__ __forceinline__ float bf16_lo(uint32_t pair) { return __uint_as_float(pair << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t pair) { return __uint_as_float(pair & 0xFFFF0000u); }
+
+// binary32 -> bf16, round to nearest, ties to even (NaN stays a quiet NaN).
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (u >> 16) | 0x40u;
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+__device__ __forceinline__ float qnan() { return __uint_as_float(0x7FC00000u); }
+
+// Sixteen bytes of a row widened to fp32: 4 floats (fp32 rows) or 8 floats (bf16 rows).
+template <bool BF16>
+struct Vec;
+template <>
+struct Vec<false> {
+  static constexpr int kElems = 4;
+  float v[4];
+  __device__ __forceinline__ void zero() { v[0] = v[1] = v[2] = v[3] = 0.f; }
+  __device__ __forceinline__ void nan() { v[0] = v[1] = v[2] = v[3] = qnan(); }
+  __device__ __forceinline__ void load(const void* p) {
+    float4 x = *reinterpret_cast<const float4*>(p);
+    v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w;
+  }
+};
+template <>
+struct Vec<true> {
+  static constexpr int kElems = 8;
+  float v[8];
+  __device__ __forceinline__ void zero() {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = 0.f;
+  }
+  __device__ __forceinline__ void nan() {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = qnan();
+  }
+  __device__ __forceinline__ void load(const void* p) {
+    uint4 x = *reinterpret_cast<const uint4*>(p);
+    v[0] = bf16_lo(x.x); v[1] = bf16_hi(x.x);
+    v[2] = bf16_lo(x.y); v[3] = bf16_hi(x.y);
+    v[4] = bf16_lo(x.z); v[5] = bf16_hi(x.z);
+    v[6] = bf16_lo(x.w); v[7] = bf16_hi(x.w);
+  }
+};
+
+__device__ __forceinline__ int64_t clamp64(int64_t x, int64_t lo, int64_t hi) {
+  return x < lo ? lo : (x > hi ? hi : x);
+}
+
+// Row-group geometry: a row of `vecs` 16-byte vectors is handled by G lanes (a power of
+// two, at most 64), each owning VPL vectors.
+struct RowGeom {
+  int G;
+  int VPL;
+};
+inline RowGeom row_geom(int64_t vecs) {
+  int G = 1;
+  while (G < 64 && G < vecs) G <<= 1;
+  int VPL = (int)((vecs + G - 1) / G);
+  return {G, VPL};
+}
+
+// ----------------------------------------------------------------------------- launchers
+// Each returns hipSuccess or the launch error.  Shapes are validated by the caller.
+
+// unique.hip
+size_t unique_workspace_bytes(int64_t n, bool need_perm);
+hipError_t launch_unique(const void* ids, bool ids64, int64_t n, const int64_t* offsets,
+                         int64_t batch, int32_t num_tables, const int64_t* row_base,
+                         int64_t modulus, int key_bits, bool key_signed, int64_t* uniq,
+                         int32_t* inverse, int32_t* num_unique, int32_t* perm,
+                         int32_t* seg_offsets, void* workspace, hipStream_t s);
+
+// embbag.hip
+hipError_t launch_embbag_fwd(const void* table, bool bf16, int64_t total_rows, int dim,
+                             const int64_t* row_base, int32_t num_tables, const void* idx,
+                             bool idx64, int64_t nnz, const int64_t* offsets, int64_t batch,
+                             float* out, int64_t sb, int64_t st, hipStream_t s);
+hipError_t launch_gather_rows(const void* table, bool bf16, int64_t total_rows, int dim,
+                              const int64_t* rows, const int32_t* num_rows, int64_t capacity,
+                              float* out, hipStream_t s);
+hipError_t launch_sparse_sgd(void* table, bool bf16, int64_t total_rows, int dim,
+                             const int64_t* uniq, const int32_t* num_unique, int64_t capacity,
+                             const float* g, float lr, hipStream_t s);
+hipError_t launch_init_table(void* table, bool bf16, int dim, int64_t row_begin,
+                             int64_t rows, float scale, uint64_t seed, hipStream_t s);
+hipError_t launch_validate_csr(const void* idx, bool idx64, int64_t nnz, const int64_t* offsets,
+                               int64_t batch, int32_t num_tables, const int64_t* row_base,
+                               int64_t total_rows, int32_t* bad, hipStream_t s);
+
+// segreduce.hip
+size_t embbag_bwd_workspace_bytes(int64_t nnz, int dim);
+hipError_t launch_embbag_bwd(const float* grad, int64_t sb, int64_t st, const int64_t* offsets,
+                             int64_t batch, int32_t num_tables, int dim, int64_t nnz,
+                             const int32_t* perm, const int32_t* inverse,
+                             const int32_t* num_unique, float* row_grads, void* workspace,
+                             hipStream_t s);
+
+// interaction.hip
+bool interaction_bf16_supported(int F, int dim);
+bool interaction_f32_supported(int F, int dim);
+hipError_t launch_interaction_fwd(const float* Z, int64_t batch, int F, int dim, bool bf16,
+                                  float* R, int64_t r_stride, hipStream_t s);
+hipError_t launch_interaction_bwd(const float* Z, const float* dR, int64_t dr_stride,
+                                  int64_t batch, int F, int dim, bool bf16, float* dZ,
+                                  hipStream_t s);
+
+}  // namespace ctr

@@ -1,0 +1,352 @@
+// embbag.hip -- row gathers on gfx950: sum-pooled embedding bags, the batch-sized matrix
+// fetch, the sparse SGD row update, the counter-based table fill and a CSR checker.
+//
+// Layout of the work: a row of the table is `vecs` 16-byte vectors (fp32: 4 values, bf16:
+// 8 values).  A group of G lanes (G a power of two, at most 64) owns one bag or one row; each
+// lane loads VPL vectors per row with 128-bit loads, so a wavefront gathers 64/G rows per
+// load instruction.  Bags are handled by one group each with their row loads unrolled
+// kUnroll deep, which keeps enough bytes in flight per wave for random 128-512 B rows.
+//
+// Pooling: "DHEN" notes, 2.1 "Feature Processing Layer" (one d-dim vector per sparse
+// feature; sum pooling is the reading taken).  Fetch into the batch-sized matrix and the
+// touched-rows-only update: "How TensorNet Supercharges Sparse Feature Training on
+// TensorFlow", "Core Optimizations" and "Synchronous Architecture".
+#include "ctr_internal.h"
+
+namespace ctr {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kUnroll = 8;
+
+template <typename TIdx, bool BF16, int G, int VPL>
+__global__ __launch_bounds__(kThreads) void embbag_fwd_kernel(
+    const char* __restrict__ table, int64_t total_rows, int64_t row_bytes, int vecs,
+    const int64_t* __restrict__ row_base, const TIdx* __restrict__ idx, int64_t nnz,
+    const int64_t* __restrict__ offsets, int64_t batch, int64_t num_bags,
+    float* __restrict__ out, int64_t sb, int64_t st) {
+  using V = Vec<BF16>;
+  constexpr int E = V::kElems;
+  const int lane = threadIdx.x & (G - 1);
+  const int64_t bag = (int64_t)blockIdx.x * (kThreads / G) + threadIdx.x / G;
+  if (bag >= num_bags) return;
+  const int64_t t = bag / batch;
+  const int64_t b = bag - t * batch;
+  const int64_t beg = clamp64(offsets[bag], 0, nnz);
+  const int64_t end = clamp64(offsets[bag + 1], beg, nnz);
+  const int64_t base = row_base ? row_base[t] : 0;
+
+  float acc[VPL][E];
+#pragma unroll
+  for (int v = 0; v < VPL; ++v)
+#pragma unroll
+    for (int e = 0; e < E; ++e) acc[v][e] = 0.f;
+
+  for (int64_t k0 = beg; k0 < end; k0 += kUnroll) {
+    V r[kUnroll][VPL];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int64_t k = k0 + u;
+      const bool live = k < end;
+      const int64_t key = live ? base + (int64_t)idx[k] : 0;
+      const bool ok = key >= 0 && key < total_rows;
+#pragma unroll
+      for (int v = 0; v < VPL; ++v) {
+        const int vi = v * G + lane;
+        if (!live || vi >= vecs)
+          r[u][v].zero();
+        else if (!ok)
+          r[u][v].nan();
+        else
+          r[u][v].load(table + key * row_bytes + (int64_t)vi * 16);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u)
+#pragma unroll
+      for (int v = 0; v < VPL; ++v)
+#pragma unroll
+        for (int e = 0; e < E; ++e) acc[v][e] += r[u][v].v[e];
+  }
+
+  float* o = out + b * sb + t * st;
+#pragma unroll
+  for (int v = 0; v < VPL; ++v) {
+    const int vi = v * G + lane;
+    if (vi >= vecs) continue;
+    float4* p = reinterpret_cast<float4*>(o + (int64_t)vi * E);
+    p[0] = make_float4(acc[v][0], acc[v][1], acc[v][2], acc[v][3]);
+    if (E == 8) p[1] = make_float4(acc[v][4 % E], acc[v][5 % E], acc[v][6 % E], acc[v][7 % E]);
+  }
+}
+
+// E[u] = W[rows[u]] widened to fp32, u < min(num_rows, capacity).
+template <bool BF16, int G, int VPL>
+__global__ __launch_bounds__(kThreads) void gather_rows_kernel(
+    const char* __restrict__ table, int64_t total_rows, int64_t row_bytes, int vecs,
+    const int64_t* __restrict__ rows, const int32_t* __restrict__ num_rows, int64_t capacity,
+    float* __restrict__ out, int64_t out_stride) {
+  using V = Vec<BF16>;
+  constexpr int E = V::kElems;
+  const int lane = threadIdx.x & (G - 1);
+  const int64_t u = (int64_t)blockIdx.x * (kThreads / G) + threadIdx.x / G;
+  const int64_t U = clamp64((int64_t)*num_rows, 0, capacity);
+  if (u >= U) return;
+  const int64_t key = rows[u];
+  const bool ok = key >= 0 && key < total_rows;
+#pragma unroll
+  for (int v = 0; v < VPL; ++v) {
+    const int vi = v * G + lane;
+    if (vi >= vecs) continue;
+    V x;
+    if (ok) x.load(table + key * row_bytes + (int64_t)vi * 16); else x.nan();
+    float4* p = reinterpret_cast<float4*>(out + u * out_stride + (int64_t)vi * E);
+    p[0] = make_float4(x.v[0], x.v[1], x.v[2], x.v[3]);
+    if (E == 8) p[1] = make_float4(x.v[4 % E], x.v[5 % E], x.v[6 % E], x.v[7 % E]);
+  }
+}
+
+// W[uniq[u]] = round(W[uniq[u]] - lr * g[u]) for u < min(num_unique, capacity).
+template <bool BF16, int G, int VPL>
+__global__ __launch_bounds__(kThreads) void sparse_sgd_kernel(
+    char* __restrict__ table, int64_t total_rows, int64_t row_bytes, int vecs,
+    const int64_t* __restrict__ uniq, const int32_t* __restrict__ num_unique, int64_t capacity,
+    const float* __restrict__ g, int64_t g_stride, float lr) {
+  using V = Vec<BF16>;
+  constexpr int E = V::kElems;
+  const int lane = threadIdx.x & (G - 1);
+  const int64_t u = (int64_t)blockIdx.x * (kThreads / G) + threadIdx.x / G;
+  const int64_t U = clamp64((int64_t)*num_unique, 0, capacity);
+  if (u >= U) return;
+  const int64_t key = uniq[u];
+  if (key < 0 || key >= total_rows) return;
+#pragma unroll
+  for (int v = 0; v < VPL; ++v) {
+    const int vi = v * G + lane;
+    if (vi >= vecs) continue;
+    char* wp = table + key * row_bytes + (int64_t)vi * 16;
+    const float4* gp = reinterpret_cast<const float4*>(g + u * g_stride + (int64_t)vi * E);
+    V w;
+    w.load(wp);
+    float gr[E];
+    {
+      const float4 a = gp[0];
+      gr[0] = a.x; gr[1] = a.y; gr[2] = a.z; gr[3] = a.w;
+      if (E == 8) {
+        const float4 c = gp[1];
+        gr[4 % E] = c.x; gr[5 % E] = c.y; gr[6 % E] = c.z; gr[7 % E] = c.w;
+      }
+    }
+    float nw[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) nw[e] = __builtin_fmaf(-lr, gr[e], w.v[e]);
+    if (BF16) {
+      uint4 q;
+      q.x = f32_to_bf16_bits(nw[0]) | (f32_to_bf16_bits(nw[1]) << 16);
+      q.y = f32_to_bf16_bits(nw[2]) | (f32_to_bf16_bits(nw[3]) << 16);
+      q.z = f32_to_bf16_bits(nw[4 % E]) | (f32_to_bf16_bits(nw[5 % E]) << 16);
+      q.w = f32_to_bf16_bits(nw[6 % E]) | (f32_to_bf16_bits(nw[7 % E]) << 16);
+      *reinterpret_cast<uint4*>(wp) = q;
+    } else {
+      *reinterpret_cast<float4*>(wp) = make_float4(nw[0], nw[1], nw[2], nw[3]);
+    }
+  }
+}
+
+// Counter-based fill: element (r, c) = fp32(2u - 1) * scale, u = top 24 bits of one
+// splitmix64 output from state seed ^ (r*dim + c) (Steele, Lea, Flood, OOPSLA 2014).
+__device__ __forceinline__ float hash_value(uint64_t seed, int64_t r, int64_t c, int dim,
+                                            float scale) {
+  uint64_t z = (seed ^ (uint64_t)(r * (int64_t)dim + c)) + 0x9E3779B97F4A7C15ull;
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  z ^= z >> 31;
+  const float u = (float)(uint32_t)(z >> 40) * (1.0f / 16777216.0f);
+  const float sgn = 2.0f * u - 1.0f;           // exact in binary32
+  return __fmul_rn(sgn, scale);
+}
+
+template <bool BF16>
+__global__ __launch_bounds__(kThreads) void init_table_kernel(char* __restrict__ table, int dim,
+                                                              int64_t row_begin, int64_t rows,
+                                                              float scale, uint64_t seed) {
+  constexpr int E = BF16 ? 8 : 4;
+  const int64_t vecs = dim / E;
+  const int64_t total = rows * vecs;
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  for (int64_t q = (int64_t)blockIdx.x * kThreads + threadIdx.x; q < total; q += stride) {
+    const int64_t r = row_begin + q / vecs;
+    const int64_t c0 = (q % vecs) * E;
+    float x[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) x[e] = hash_value(seed, r, c0 + e, dim, scale);
+    char* p = table + (r * dim + c0) * (BF16 ? 2 : 4);
+    if (BF16) {
+      uint4 w;
+      w.x = f32_to_bf16_bits(x[0]) | (f32_to_bf16_bits(x[1]) << 16);
+      w.y = f32_to_bf16_bits(x[2]) | (f32_to_bf16_bits(x[3]) << 16);
+      w.z = f32_to_bf16_bits(x[4 % E]) | (f32_to_bf16_bits(x[5 % E]) << 16);
+      w.w = f32_to_bf16_bits(x[6 % E]) | (f32_to_bf16_bits(x[7 % E]) << 16);
+      *reinterpret_cast<uint4*>(p) = w;
+    } else {
+      *reinterpret_cast<float4*>(p) = make_float4(x[0], x[1], x[2], x[3]);
+    }
+  }
+}
+
+template <typename TIdx>
+__global__ __launch_bounds__(kThreads) void validate_csr_kernel(
+    const TIdx* __restrict__ idx, int64_t nnz, const int64_t* __restrict__ offsets,
+    int64_t batch, int32_t num_tables, const int64_t* __restrict__ row_base, int64_t total_rows,
+    int32_t* __restrict__ bad) {
+  const int64_t nb = (int64_t)num_tables * batch;
+  const int64_t s = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  int32_t errs = 0;
+  if (s == 0 && offsets[0] != 0) ++errs;
+  if (s == 0 && offsets[nb] != nnz) ++errs;
+  if (s < nb) {
+    const int64_t a = offsets[s], e = offsets[s + 1];
+    if (e < a) {
+      ++errs;
+    } else {
+      const int64_t t = s / batch;
+      const int64_t rows = row_base ? row_base[t + 1] - row_base[t] : total_rows;
+      const int64_t lo = clamp64(a, 0, nnz), hi = clamp64(e, 0, nnz);
+      for (int64_t k = lo; k < hi; ++k) {
+        const int64_t v = (int64_t)idx[k];
+        if (v < 0 || v >= rows) ++errs;
+      }
+    }
+  }
+  if (errs) atomicAdd(bad, errs);
+}
+
+}  // namespace
+
+// ----------------------------------------------------------------------------- launchers
+#define CTR_DISPATCH_G_VPL(G_, VPL_, ...)                                   \
+  do {                                                                      \
+    switch (G_) {                                                           \
+      case 1: { constexpr int G = 1, VPL = 1; __VA_ARGS__; } break;         \
+      case 2: { constexpr int G = 2, VPL = 1; __VA_ARGS__; } break;         \
+      case 4: { constexpr int G = 4, VPL = 1; __VA_ARGS__; } break;         \
+      case 8: { constexpr int G = 8, VPL = 1; __VA_ARGS__; } break;         \
+      case 16: { constexpr int G = 16, VPL = 1; __VA_ARGS__; } break;       \
+      case 32: { constexpr int G = 32, VPL = 1; __VA_ARGS__; } break;       \
+      default:                                                              \
+        if ((VPL_) == 1) { constexpr int G = 64, VPL = 1; __VA_ARGS__; }    \
+        else if ((VPL_) == 2) { constexpr int G = 64, VPL = 2; __VA_ARGS__; } \
+        else { constexpr int G = 64, VPL = 4; __VA_ARGS__; }                \
+        break;                                                              \
+    }                                                                       \
+  } while (0)
+
+hipError_t launch_embbag_fwd(const void* table, bool bf16, int64_t total_rows, int dim,
+                             const int64_t* row_base, int32_t num_tables, const void* idx,
+                             bool idx64, int64_t nnz, const int64_t* offsets, int64_t batch,
+                             float* out, int64_t sb, int64_t st, hipStream_t s) {
+  const int E = bf16 ? 8 : 4;
+  const int vecs = dim / E;
+  const RowGeom rg = row_geom(vecs);
+  const int64_t row_bytes = (int64_t)dim * (bf16 ? 2 : 4);
+  const int64_t num_bags = (int64_t)num_tables * batch;
+  if (num_bags == 0) return hipSuccess;
+  const char* tb = static_cast<const char*>(table);
+  CTR_DISPATCH_G_VPL(rg.G, rg.VPL, {
+    const int64_t blocks = (num_bags + (kThreads / G) - 1) / (kThreads / G);
+    if (bf16) {
+      if (idx64)
+        embbag_fwd_kernel<int64_t, true, G, VPL><<<(unsigned)blocks, kThreads, 0, s>>>(
+            tb, total_rows, row_bytes, vecs, row_base, (const int64_t*)idx, nnz, offsets,
+            batch, num_bags, out, sb, st);
+      else
+        embbag_fwd_kernel<int32_t, true, G, VPL><<<(unsigned)blocks, kThreads, 0, s>>>(
+            tb, total_rows, row_bytes, vecs, row_base, (const int32_t*)idx, nnz, offsets,
+            batch, num_bags, out, sb, st);
+    } else {
+      if (idx64)
+        embbag_fwd_kernel<int64_t, false, G, VPL><<<(unsigned)blocks, kThreads, 0, s>>>(
+            tb, total_rows, row_bytes, vecs, row_base, (const int64_t*)idx, nnz, offsets,
+            batch, num_bags, out, sb, st);
+      else
+        embbag_fwd_kernel<int32_t, false, G, VPL><<<(unsigned)blocks, kThreads, 0, s>>>(
+            tb, total_rows, row_bytes, vecs, row_base, (const int32_t*)idx, nnz, offsets,
+            batch, num_bags, out, sb, st);
+    }
+  });
+  return hipGetLastError();
+}
+
+hipError_t launch_gather_rows(const void* table, bool bf16, int64_t total_rows, int dim,
+                              const int64_t* rows, const int32_t* num_rows, int64_t capacity,
+                              float* out, hipStream_t s) {
+  if (capacity == 0) return hipSuccess;
+  const int E = bf16 ? 8 : 4;
+  const int vecs = dim / E;
+  const RowGeom rg = row_geom(vecs);
+  const int64_t row_bytes = (int64_t)dim * (bf16 ? 2 : 4);
+  const char* tb = static_cast<const char*>(table);
+  CTR_DISPATCH_G_VPL(rg.G, rg.VPL, {
+    const int64_t blocks = (capacity + (kThreads / G) - 1) / (kThreads / G);
+    if (bf16)
+      gather_rows_kernel<true, G, VPL><<<(unsigned)blocks, kThreads, 0, s>>>(
+          tb, total_rows, row_bytes, vecs, rows, num_rows, capacity, out, dim);
+    else
+      gather_rows_kernel<false, G, VPL><<<(unsigned)blocks, kThreads, 0, s>>>(
+          tb, total_rows, row_bytes, vecs, rows, num_rows, capacity, out, dim);
+  });
+  return hipGetLastError();
+}
+
+hipError_t launch_sparse_sgd(void* table, bool bf16, int64_t total_rows, int dim,
+                             const int64_t* uniq, const int32_t* num_unique, int64_t capacity,
+                             const float* g, float lr, hipStream_t s) {
+  if (capacity == 0) return hipSuccess;
+  const int E = bf16 ? 8 : 4;
+  const int vecs = dim / E;
+  const RowGeom rg = row_geom(vecs);
+  const int64_t row_bytes = (int64_t)dim * (bf16 ? 2 : 4);
+  char* tb = static_cast<char*>(table);
+  CTR_DISPATCH_G_VPL(rg.G, rg.VPL, {
+    const int64_t blocks = (capacity + (kThreads / G) - 1) / (kThreads / G);
+    if (bf16)
+      sparse_sgd_kernel<true, G, VPL><<<(unsigned)blocks, kThreads, 0, s>>>(
+          tb, total_rows, row_bytes, vecs, uniq, num_unique, capacity, g, dim, lr);
+    else
+      sparse_sgd_kernel<false, G, VPL><<<(unsigned)blocks, kThreads, 0, s>>>(
+          tb, total_rows, row_bytes, vecs, uniq, num_unique, capacity, g, dim, lr);
+  });
+  return hipGetLastError();
+}
+
+hipError_t launch_init_table(void* table, bool bf16, int dim, int64_t row_begin, int64_t rows,
+                             float scale, uint64_t seed, hipStream_t s) {
+  if (rows == 0) return hipSuccess;
+  const int E = bf16 ? 8 : 4;
+  const int64_t total = rows * (dim / E);
+  int64_t blocks = (total + kThreads - 1) / kThreads;
+  if (blocks > 65536) blocks = 65536;
+  if (bf16)
+    init_table_kernel<true><<<(unsigned)blocks, kThreads, 0, s>>>(
+        static_cast<char*>(table), dim, row_begin, rows, scale, seed);
+  else
+    init_table_kernel<false><<<(unsigned)blocks, kThreads, 0, s>>>(
+        static_cast<char*>(table), dim, row_begin, rows, scale, seed);
+  return hipGetLastError();
+}
+
+hipError_t launch_validate_csr(const void* idx, bool idx64, int64_t nnz, const int64_t* offsets,
+                               int64_t batch, int32_t num_tables, const int64_t* row_base,
+                               int64_t total_rows, int32_t* bad, hipStream_t s) {
+  const int64_t nb = (int64_t)num_tables * batch;
+  const int64_t blocks = (nb + kThreads) / kThreads;   // at least one block for the ends
+  if (idx64)
+    validate_csr_kernel<int64_t><<<(unsigned)blocks, kThreads, 0, s>>>(
+        (const int64_t*)idx, nnz, offsets, batch, num_tables, row_base, total_rows, bad);
+  else
+    validate_csr_kernel<int32_t><<<(unsigned)blocks, kThreads, 0, s>>>(
+        (const int32_t*)idx, nnz, offsets, batch, num_tables, row_base, total_rows, bad);
+  return hipGetLastError();
+}
+
+}  // namespace ctr

@@ -1,0 +1,397 @@
+// segreduce.hip -- backward of sum pooling on gfx950: per-occurrence gradients summed onto
+// the batch's distinct rows ("How TensorNet Supercharges Sparse Feature Training on
+// TensorFlow", "Synchronous Architecture": only rows present in the batch get anything).
+//
+// Inputs come from the unique step: perm (sorted position -> occurrence) and inverse
+// (occurrence -> distinct-row index u).  Three steps, all deterministic, no atomics:
+//   1. bag_of[i]   bag of every occurrence (a wave expands 64 bags, lanes binary-search the
+//                  64 bag ends with shuffles, stores are coalesced)
+//   2. src[p]      (u, bag) of sorted position p
+//   3. a reduce-by-key over the sorted sequence in fixed chunks, so that a row hit a million
+//      times costs the same as a million rows hit once.  A workgroup owns a chunk of
+//      S*kPerSlot positions; each G-lane slot sums kPerSlot consecutive positions serially
+//      (G lanes x 16 B per row) and writes finished segments straight to row_grads; the
+//      pieces of segments that cross slot edges are joined in LDS; pieces that cross the
+//      chunk edges go out as at most two carries per chunk.  The carries (key, row) form a
+//      sequence of the same kind, reduced by the same kernel, until one chunk is left:
+//      a tree of fixed shape whose depth is ceil(log_chunk(n)).
+#include "ctr_internal.h"
+
+namespace ctr {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kPerSlot = 64;     // positions summed serially by one slot
+constexpr int kUnroll = 8;
+
+__global__ __launch_bounds__(kThreads) void bag_of_kernel(const int64_t* __restrict__ offsets,
+                                                          int64_t num_bags, int64_t nnz,
+                                                          int32_t* __restrict__ bag_of) {
+  const int lane = threadIdx.x & 63;
+  const int64_t wave = ((int64_t)blockIdx.x * kThreads + threadIdx.x) >> 6;
+  const int64_t s0 = wave * 64;
+  if (s0 >= num_bags) return;
+  const int64_t s = s0 + lane;
+  // end of bag s0+lane (bags past the last one end at +inf)
+  const int64_t my_end = s < num_bags ? clamp64(offsets[s + 1], 0, nnz) : INT64_MAX;
+  const int64_t beg = clamp64(offsets[s0], 0, nnz);
+  const int64_t last = s0 + 64 < num_bags ? s0 + 64 : num_bags;
+  const int64_t end = clamp64(offsets[last], beg, nnz);
+  for (int64_t i0 = beg; i0 < end; i0 += 64) {
+    const int64_t i = i0 + lane;
+    // l = number of bags among the 64 whose end is <= i, i.e. the bag that holds i
+    int l = 0;
+#pragma unroll
+    for (int step = 32; step > 0; step >>= 1) {
+      const int64_t e = __shfl(my_end, l + step - 1, 64);
+      if (e <= i) l += step;
+    }
+    if (i < end) bag_of[i] = (int32_t)(s0 + l);
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void seg_src_kernel(const int32_t* __restrict__ perm,
+                                                           const int32_t* __restrict__ inverse,
+                                                           const int32_t* __restrict__ bag_of,
+                                                           int64_t n, int2* __restrict__ src) {
+  const int64_t p = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (p >= n) return;
+  const int32_t i = perm[p];
+  int2 r = make_int2(-1, 0);
+  if (i >= 0 && (int64_t)i < n) r = make_int2(inverse[i], bag_of[i]);
+  src[p] = r;
+}
+
+struct L0Source {
+  const int2* src;
+  const float* grad;
+  int64_t sb, st, batch, num_bags;
+  __device__ __forceinline__ int32_t key(int64_t p) const { return src[p].x; }
+};
+
+struct LnSource {
+  const int32_t* keys;
+  const float* rows;
+  int dim;
+  __device__ __forceinline__ int32_t key(int64_t p) const { return keys[p]; }
+};
+
+template <int VPL>
+struct RowAcc {
+  float v[VPL][4];
+  __device__ __forceinline__ void zero() {
+#pragma unroll
+    for (int a = 0; a < VPL; ++a) v[a][0] = v[a][1] = v[a][2] = v[a][3] = 0.f;
+  }
+};
+
+// Key of the nearest real entry before position q in a carry sequence: a run of one key
+// never holds two consecutive empty (-1) entries, so looking two back is enough.
+template <bool L0, typename Src>
+__device__ __forceinline__ int32_t key_before(const Src& S, int64_t q) {
+  if (q <= 0) return -1;
+  const int32_t k = S.key(q - 1);
+  if (L0 || k != -1) return k;
+  return q >= 2 ? S.key(q - 2) : -1;
+}
+template <bool L0, typename Src>
+__device__ __forceinline__ int32_t key_after(const Src& S, int64_t q, int64_t n) {
+  if (q >= n) return -1;
+  const int32_t k = S.key(q);
+  if (L0 || k != -1) return k;
+  return q + 1 < n ? S.key(q + 1) : -1;
+}
+
+template <int G, int VPL>
+struct SegSmem {
+  float first_row[kThreads / G][G * VPL * 4];
+  float last_row[kThreads / G][G * VPL * 4];
+  int32_t first_key[kThreads / G];
+  int32_t first_cont[kThreads / G];
+  int32_t last_key[kThreads / G];
+  int32_t wg_first_key;
+  int32_t wg_last_key;
+};
+
+// One reduce-by-key level.  L0: entries are sorted positions of the occurrences (keys from
+// src, rows gathered from grad); otherwise entries are carries (keys may be -1 = empty).
+template <bool L0, int G, int VPL, typename Src>
+__global__ __launch_bounds__(kThreads) void segreduce_kernel(
+    Src S, int64_t n, int dim, int64_t capacity, float* __restrict__ row_grads,
+    int32_t* __restrict__ out_keys, float* __restrict__ out_rows) {
+  constexpr int kSlots = kThreads / G;
+  constexpr int kW = G * VPL * 4;              // floats per slot row in LDS
+  __shared__ SegSmem<G, VPL> sm;
+  const int lane = threadIdx.x & (G - 1);
+  const int slot = threadIdx.x / G;
+  const int64_t chunk0 = (int64_t)blockIdx.x * kSlots * kPerSlot;
+  const int64_t q0 = chunk0 + (int64_t)slot * kPerSlot;
+  const int64_t q1 = q0 + kPerSlot < n ? q0 + kPerSlot : n;
+  const int64_t chunk1 = chunk0 + (int64_t)kSlots * kPerSlot < n ? chunk0 + (int64_t)kSlots * kPerSlot : n;
+
+  // column of vector a of this lane
+  auto col = [&](int a) { return (a * G + lane) * 4; };
+  auto write_row = [&](float* dst, const RowAcc<VPL>& r) {
+#pragma unroll
+    for (int a = 0; a < VPL; ++a) {
+      const int c = col(a);
+      if (c < dim)
+        *reinterpret_cast<float4*>(dst + c) = make_float4(r.v[a][0], r.v[a][1], r.v[a][2], r.v[a][3]);
+    }
+  };
+  auto emit_complete = [&](int32_t u, const RowAcc<VPL>& r) {
+    if (u >= 0 && (int64_t)u < capacity) write_row(row_grads + (int64_t)u * dim, r);
+  };
+
+  int32_t fkey = -1, fcont = 0, lkey = -1;
+  if (q0 < n) {
+    const int32_t kb = key_before<L0>(S, q0);
+    int32_t cur = -1;
+    bool cur_before = false;
+    bool first_seen = false;
+    RowAcc<VPL> acc;
+    acc.zero();
+    for (int64_t p0 = q0; p0 < q1; p0 += kUnroll) {
+      int32_t kk[kUnroll];
+      float4 rv[kUnroll][VPL];
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        const int64_t p = p0 + u;
+        kk[u] = -1;
+        const float* rp = nullptr;
+        if (p < q1) {
+          if constexpr (L0) {
+            const int2 sr = S.src[p];
+            kk[u] = sr.x;
+            int64_t bag = sr.y;
+            if (bag < 0 || bag >= S.num_bags) bag = 0;
+            const int64_t t = bag / S.batch, b = bag - t * S.batch;
+            rp = S.grad + b * S.sb + t * S.st;
+          } else {
+            kk[u] = S.keys[p];
+            rp = S.rows + p * (int64_t)S.dim;
+          }
+        }
+#pragma unroll
+        for (int a = 0; a < VPL; ++a) {
+          const int c = col(a);
+          if (rp && kk[u] != -1 && c < dim)
+            rv[u][a] = *reinterpret_cast<const float4*>(rp + c);
+          else
+            rv[u][a] = make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        if (kk[u] == -1) continue;
+        if (kk[u] != cur) {
+          if (cur != -1) {             // previous segment ended inside this slot
+            if (cur_before) {
+              fkey = cur;
+              fcont = 0;
+#pragma unroll
+              for (int a = 0; a < VPL; ++a)
+                *reinterpret_cast<float4*>(&sm.first_row[slot][col(a)]) =
+                    make_float4(acc.v[a][0], acc.v[a][1], acc.v[a][2], acc.v[a][3]);
+            } else {
+              emit_complete(cur, acc);
+            }
+          }
+          cur = kk[u];
+          cur_before = !first_seen && (kk[u] == kb);
+          first_seen = true;
+          acc.zero();
+        }
+#pragma unroll
+        for (int a = 0; a < VPL; ++a) {
+          acc.v[a][0] += rv[u][a].x;
+          acc.v[a][1] += rv[u][a].y;
+          acc.v[a][2] += rv[u][a].z;
+          acc.v[a][3] += rv[u][a].w;
+        }
+      }
+    }
+    if (cur != -1) {
+      const bool cont = key_after<L0>(S, q1, n) == cur;
+      if (cur_before) {
+        fkey = cur;
+        fcont = cont ? 1 : 0;
+#pragma unroll
+        for (int a = 0; a < VPL; ++a)
+          *reinterpret_cast<float4*>(&sm.first_row[slot][col(a)]) =
+              make_float4(acc.v[a][0], acc.v[a][1], acc.v[a][2], acc.v[a][3]);
+      } else if (cont) {
+        lkey = cur;
+#pragma unroll
+        for (int a = 0; a < VPL; ++a)
+          *reinterpret_cast<float4*>(&sm.last_row[slot][col(a)]) =
+              make_float4(acc.v[a][0], acc.v[a][1], acc.v[a][2], acc.v[a][3]);
+      } else {
+        emit_complete(cur, acc);
+      }
+    }
+  }
+  if (lane == 0) {
+    sm.first_key[slot] = fkey;
+    sm.first_cont[slot] = fcont;
+    sm.last_key[slot] = lkey;
+  }
+  if (threadIdx.x == 0) {
+    sm.wg_first_key = -1;
+    sm.wg_last_key = -1;
+  }
+  __syncthreads();
+
+  // Join the pieces of segments that cross slot edges.  The owner of a segment is the slot
+  // where it starts (its "last" piece) or, for the segment that started before this chunk,
+  // slot 0.  Walking right adds the next slots' "first" pieces until one does not continue.
+  const int64_t carry_base = 2 * (int64_t)blockIdx.x;
+  auto walk = [&](int32_t u, int start_slot, RowAcc<VPL>& acc) -> bool {
+    int j = start_slot;
+    while (j < kSlots) {
+      if (sm.first_key[j] != u) return true;    // defensive: cannot happen on valid input
+#pragma unroll
+      for (int a = 0; a < VPL; ++a) {
+        const float4 x = *reinterpret_cast<const float4*>(&sm.first_row[j][col(a)]);
+        acc.v[a][0] += x.x; acc.v[a][1] += x.y; acc.v[a][2] += x.z; acc.v[a][3] += x.w;
+      }
+      if (!sm.first_cont[j]) return true;       // ended inside slot j
+      ++j;
+    }
+    return false;                               // runs past the end of the chunk
+  };
+  (void)chunk1;
+  if (slot == 0 && sm.first_key[0] != -1) {
+    // started before this chunk: always leaves as the chunk's first carry
+    const int32_t u = sm.first_key[0];
+    RowAcc<VPL> acc;
+#pragma unroll
+    for (int a = 0; a < VPL; ++a) {
+      const float4 x = *reinterpret_cast<const float4*>(&sm.first_row[0][col(a)]);
+      acc.v[a][0] = x.x; acc.v[a][1] = x.y; acc.v[a][2] = x.z; acc.v[a][3] = x.w;
+    }
+    if (sm.first_cont[0]) walk(u, 1, acc);
+    write_row(out_rows + carry_base * dim, acc);
+    if (lane == 0) sm.wg_first_key = u;
+  }
+  if (sm.last_key[slot] != -1) {
+    const int32_t u = sm.last_key[slot];
+    RowAcc<VPL> acc;
+#pragma unroll
+    for (int a = 0; a < VPL; ++a) {
+      const float4 x = *reinterpret_cast<const float4*>(&sm.last_row[slot][col(a)]);
+      acc.v[a][0] = x.x; acc.v[a][1] = x.y; acc.v[a][2] = x.z; acc.v[a][3] = x.w;
+    }
+    if (walk(u, slot + 1, acc)) {
+      emit_complete(u, acc);
+    } else {
+      write_row(out_rows + (carry_base + 1) * dim, acc);
+      if (lane == 0) sm.wg_last_key = u;
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x == 0 && out_keys) {
+    out_keys[carry_base] = sm.wg_first_key;
+    out_keys[carry_base + 1] = sm.wg_last_key;
+  }
+  (void)kW;
+}
+
+inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+struct BwdWs {
+  int32_t* bag_of;
+  int2* src;
+  int32_t* ckeys[2];
+  float* crows[2];
+  size_t bytes;
+};
+
+int64_t chunk_positions(int dim) {
+  const RowGeom rg = row_geom(dim / 4);
+  return (int64_t)(kThreads / rg.G) * kPerSlot;
+}
+
+BwdWs carve(void* base, int64_t n, int dim) {
+  BwdWs w{};
+  size_t off = 0;
+  char* b = static_cast<char*>(base);
+  auto take = [&](size_t sz) {
+    char* p = b ? b + off : nullptr;
+    off += align256(sz);
+    return p;
+  };
+  const int64_t chunk = chunk_positions(dim);
+  const int64_t c1 = 2 * ((n + chunk - 1) / chunk);   // carries out of level 0 (largest)
+  w.bag_of = reinterpret_cast<int32_t*>(take(sizeof(int32_t) * (size_t)n));
+  w.src = reinterpret_cast<int2*>(take(sizeof(int2) * (size_t)n));
+  for (int k = 0; k < 2; ++k) {
+    w.ckeys[k] = reinterpret_cast<int32_t*>(take(sizeof(int32_t) * (size_t)(c1 + 2)));
+    w.crows[k] = reinterpret_cast<float*>(take(sizeof(float) * (size_t)(c1 + 2) * dim));
+  }
+  w.bytes = off;
+  return w;
+}
+
+}  // namespace
+
+size_t embbag_bwd_workspace_bytes(int64_t nnz, int dim) { return carve(nullptr, nnz, dim).bytes; }
+
+#define CTR_SEG_DISPATCH(G_, VPL_, ...)                                     \
+  do {                                                                      \
+    switch (G_) {                                                           \
+      case 1: { constexpr int G = 1, VPL = 1; __VA_ARGS__; } break;         \
+      case 2: { constexpr int G = 2, VPL = 1; __VA_ARGS__; } break;         \
+      case 4: { constexpr int G = 4, VPL = 1; __VA_ARGS__; } break;         \
+      case 8: { constexpr int G = 8, VPL = 1; __VA_ARGS__; } break;         \
+      case 16: { constexpr int G = 16, VPL = 1; __VA_ARGS__; } break;       \
+      case 32: { constexpr int G = 32, VPL = 1; __VA_ARGS__; } break;       \
+      default:                                                              \
+        if ((VPL_) == 1) { constexpr int G = 64, VPL = 1; __VA_ARGS__; }    \
+        else if ((VPL_) == 2) { constexpr int G = 64, VPL = 2; __VA_ARGS__; } \
+        else { constexpr int G = 64, VPL = 4; __VA_ARGS__; }                \
+        break;                                                              \
+    }                                                                       \
+  } while (0)
+
+hipError_t launch_embbag_bwd(const float* grad, int64_t sb, int64_t st, const int64_t* offsets,
+                             int64_t batch, int32_t num_tables, int dim, int64_t nnz,
+                             const int32_t* perm, const int32_t* inverse,
+                             const int32_t* num_unique, float* row_grads, void* workspace,
+                             hipStream_t s) {
+  (void)num_unique;
+  if (nnz == 0) return hipSuccess;
+  BwdWs w = carve(workspace, nnz, dim);
+  const int64_t num_bags = (int64_t)num_tables * batch;
+
+  {
+    const int64_t waves = (num_bags + 63) / 64;
+    const int64_t blocks = (waves + 3) / 4;
+    bag_of_kernel<<<(unsigned)blocks, kThreads, 0, s>>>(offsets, num_bags, nnz, w.bag_of);
+  }
+  seg_src_kernel<<<(unsigned)((nnz + kThreads - 1) / kThreads), kThreads, 0, s>>>(
+      perm, inverse, w.bag_of, nnz, w.src);
+
+  const RowGeom rg = row_geom(dim / 4);
+  const int64_t chunk = chunk_positions(dim);
+  CTR_SEG_DISPATCH(rg.G, rg.VPL, {
+    int64_t len = nnz;
+    int64_t blocks = (len + chunk - 1) / chunk;
+    int cur = 0;
+    L0Source s0{w.src, grad, sb, st, batch, num_bags};
+    segreduce_kernel<true, G, VPL, L0Source><<<(unsigned)blocks, kThreads, 0, s>>>(
+        s0, len, dim, nnz, row_grads, blocks > 1 ? w.ckeys[cur] : nullptr, w.crows[cur]);
+    while (blocks > 1) {
+      len = 2 * blocks;
+      blocks = (len + chunk - 1) / chunk;
+      LnSource sn{w.ckeys[cur], w.crows[cur], dim};
+      segreduce_kernel<false, G, VPL, LnSource><<<(unsigned)blocks, kThreads, 0, s>>>(
+          sn, len, dim, nnz, row_grads, blocks > 1 ? w.ckeys[cur ^ 1] : nullptr,
+          w.crows[cur ^ 1]);
+      cur ^= 1;
+    }
+  });
+  return hipGetLastError();
+}
+
+}  // namespace ctr

@@ -1,0 +1,240 @@
+"""Thin Python binding of libctr (include/ctr.h), one function per C entry point, same names.
+
+Only argument marshalling happens here: torch tensors provide device memory and the current
+stream, every step of the computation runs in the HIP kernels of libctr.so.  There is no CPU
+fallback: if the library is missing or fails to load, the first call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence, Tuple
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libctr.so")
+
+CTR_OK, CTR_ERR_INVALID_ARGUMENT, CTR_ERR_UNSUPPORTED, CTR_ERR_WORKSPACE_TOO_SMALL, CTR_ERR_HIP = range(5)
+CTR_F32, CTR_BF16 = 0, 1
+CTR_I32, CTR_I64 = 0, 1
+
+EXPORTED = [
+    "ctr_version", "ctr_status_string", "ctr_last_error", "ctr_unique_ids", "ctr_gather_rows",
+    "ctr_embbag_fwd", "ctr_embbag_bwd", "ctr_sparse_sgd", "ctr_dot_interaction_fwd",
+    "ctr_dot_interaction_bwd", "ctr_init_table_hash", "ctr_validate_csr",
+]
+
+_lib = None
+
+
+class CtrError(RuntimeError):
+    def __init__(self, fn: str, status: int, msg: str):
+        super().__init__("%s failed: %s (%s)" % (fn, _status_name(status), msg))
+        self.status = status
+
+
+def _status_name(s: int) -> str:
+    return ["CTR_OK", "CTR_ERR_INVALID_ARGUMENT", "CTR_ERR_UNSUPPORTED",
+            "CTR_ERR_WORKSPACE_TOO_SMALL", "CTR_ERR_HIP"][s] if 0 <= s < 5 else "CTR_ERR_UNKNOWN"
+
+
+def load() -> ctypes.CDLL:
+    """Loads libctr.so from the package directory (built by build.py); raises if absent."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError("libctr.so is not built (run python -m sparse_embedding_lookup_amd.build)")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, i32, i64, u64, f32, sz = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64,
+                                 ctypes.c_uint64, ctypes.c_float, ctypes.c_size_t)
+    PS = ctypes.POINTER(ctypes.c_size_t)
+    sig = {
+        "ctr_version": (i32, []),
+        "ctr_status_string": (ctypes.c_char_p, [i32]),
+        "ctr_last_error": (ctypes.c_char_p, []),
+        "ctr_unique_ids": (i32, [P, i32, i64, P, i64, i32, P, i64, i64, P, P, P, P, P, P, PS, P]),
+        "ctr_gather_rows": (i32, [P, i32, i64, i32, P, P, i64, P, P]),
+        "ctr_embbag_fwd": (i32, [P, i32, i64, i32, P, i32, P, i32, i64, P, i64, P, i64, i64, P]),
+        "ctr_embbag_bwd": (i32, [P, i64, i64, P, i64, i32, i32, i64, P, P, P, P, P, PS, P]),
+        "ctr_sparse_sgd": (i32, [P, i32, i64, i32, P, P, i64, P, f32, P]),
+        "ctr_dot_interaction_fwd": (i32, [P, i64, i32, i32, i32, P, i64, P]),
+        "ctr_dot_interaction_bwd": (i32, [P, P, i64, i64, i32, i32, i32, P, P]),
+        "ctr_init_table_hash": (i32, [P, i32, i32, P, i32, u64, P]),
+        "ctr_validate_csr": (i32, [P, i32, i64, P, i64, i32, P, i64, P, P]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _check(fn: str, status: int) -> None:
+    if status != CTR_OK:
+        raise CtrError(fn, status, load().ctr_last_error().decode())
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return CTR_F32
+    if t.dtype == torch.bfloat16:
+        return CTR_BF16
+    raise TypeError("table dtype must be float32 or bfloat16")
+
+
+def _index_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.int64:
+        return CTR_I64
+    if t.dtype == torch.int32:
+        return CTR_I32
+    raise TypeError("index dtype must be int32 or int64")
+
+
+def _workspace(nbytes: int, device) -> torch.Tensor:
+    return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+
+
+# ----------------------------------------------------------------------------- entry points
+def ctr_version() -> int:
+    return int(load().ctr_version())
+
+
+def ctr_unique_ids(ids: torch.Tensor, *, offsets: Optional[torch.Tensor] = None, batch: int = 0,
+                   num_tables: int = 0, row_base: Optional[torch.Tensor] = None,
+                   total_rows: int = 0, key_modulus: int = 0, want_perm: bool = True,
+                   want_seg: bool = True, workspace: Optional[torch.Tensor] = None, stream=None
+                   ) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor, Optional[torch.Tensor],
+                              Optional[torch.Tensor]]:
+    """Returns (uniq int64[n], inverse int32[n], num_unique int32[1], perm, seg_offsets);
+    only the first num_unique entries of uniq (and num_unique+1 of seg_offsets) are set."""
+    lib = load()
+    n = ids.numel()
+    dev = ids.device
+    uniq = torch.empty(max(n, 1), dtype=torch.int64, device=dev)
+    inv = torch.empty(max(n, 1), dtype=torch.int32, device=dev)
+    nu = torch.empty(1, dtype=torch.int32, device=dev)
+    perm = torch.empty(max(n, 1), dtype=torch.int32, device=dev) if want_perm else None
+    seg = torch.empty(n + 1, dtype=torch.int32, device=dev) if want_seg else None
+    args = (_ptr(ids), _index_code(ids), n, _ptr(offsets), batch, num_tables, _ptr(row_base),
+            total_rows, key_modulus)
+    wsb = ctypes.c_size_t(0)
+    _check("ctr_unique_ids", lib.ctr_unique_ids(*args, None, None, None, None, None, None,
+                                                ctypes.byref(wsb), None))
+    ws = workspace if workspace is not None and workspace.numel() >= wsb.value else _workspace(wsb.value, dev)
+    wsb = ctypes.c_size_t(ws.numel())
+    _check("ctr_unique_ids", lib.ctr_unique_ids(*args, _ptr(uniq), _ptr(inv), _ptr(nu),
+                                                _ptr(perm), _ptr(seg), _ptr(ws),
+                                                ctypes.byref(wsb), _stream(stream)))
+    return uniq[:n], inv[:n], nu, (perm[:n] if perm is not None else None), seg
+
+
+def ctr_gather_rows(table: torch.Tensor, rows: torch.Tensor, num_rows: torch.Tensor,
+                    capacity: int, out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    lib = load()
+    total_rows, dim = table.shape
+    if out is None:
+        out = torch.empty((max(capacity, 1), dim), dtype=torch.float32, device=table.device)
+    _check("ctr_gather_rows", lib.ctr_gather_rows(_ptr(table), _dtype_code(table), total_rows, dim,
+                                                  _ptr(rows), _ptr(num_rows), capacity, _ptr(out),
+                                                  _stream(stream)))
+    return out
+
+
+def ctr_embbag_fwd(table: torch.Tensor, indices: torch.Tensor, offsets: torch.Tensor,
+                   batch: int, num_tables: int, out: torch.Tensor, out_stride_b: int,
+                   out_stride_t: int, row_base: Optional[torch.Tensor] = None,
+                   stream=None) -> torch.Tensor:
+    lib = load()
+    total_rows, dim = table.shape
+    _check("ctr_embbag_fwd", lib.ctr_embbag_fwd(
+        _ptr(table), _dtype_code(table), total_rows, dim, _ptr(row_base), num_tables,
+        _ptr(indices), _index_code(indices), indices.numel(), _ptr(offsets), batch, _ptr(out),
+        out_stride_b, out_stride_t, _stream(stream)))
+    return out
+
+
+def ctr_embbag_bwd(grad: torch.Tensor, grad_stride_b: int, grad_stride_t: int,
+                   offsets: torch.Tensor, batch: int, num_tables: int, dim: int,
+                   perm: torch.Tensor, inverse: torch.Tensor, num_unique: torch.Tensor,
+                   row_grads: Optional[torch.Tensor] = None,
+                   workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    lib = load()
+    nnz = perm.numel()
+    dev = grad.device
+    if row_grads is None:
+        row_grads = torch.empty((max(nnz, 1), dim), dtype=torch.float32, device=dev)
+    args = (_ptr(grad), grad_stride_b, grad_stride_t, _ptr(offsets), batch, num_tables, dim, nnz,
+            _ptr(perm), _ptr(inverse), _ptr(num_unique), _ptr(row_grads))
+    wsb = ctypes.c_size_t(0)
+    _check("ctr_embbag_bwd", lib.ctr_embbag_bwd(*args, None, ctypes.byref(wsb), None))
+    ws = workspace if workspace is not None and workspace.numel() >= wsb.value else _workspace(wsb.value, dev)
+    wsb = ctypes.c_size_t(ws.numel())
+    _check("ctr_embbag_bwd", lib.ctr_embbag_bwd(*args, _ptr(ws), ctypes.byref(wsb), _stream(stream)))
+    return row_grads
+
+
+def ctr_sparse_sgd(table: torch.Tensor, uniq: torch.Tensor, num_unique: torch.Tensor,
+                   capacity: int, row_grads: torch.Tensor, lr: float, stream=None) -> None:
+    lib = load()
+    total_rows, dim = table.shape
+    _check("ctr_sparse_sgd", lib.ctr_sparse_sgd(_ptr(table), _dtype_code(table), total_rows, dim,
+                                                _ptr(uniq), _ptr(num_unique), capacity,
+                                                _ptr(row_grads), ctypes.c_float(lr),
+                                                _stream(stream)))
+
+
+def ctr_dot_interaction_fwd(Z: torch.Tensor, compute: int = CTR_F32,
+                            R: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    lib = load()
+    B, F, d = Z.shape
+    P = F * (F - 1) // 2
+    if R is None:
+        R = torch.empty((B, d + P), dtype=torch.float32, device=Z.device)
+    _check("ctr_dot_interaction_fwd", lib.ctr_dot_interaction_fwd(
+        _ptr(Z), B, F, d, compute, _ptr(R), R.stride(0), _stream(stream)))
+    return R
+
+
+def ctr_dot_interaction_bwd(Z: torch.Tensor, dR: torch.Tensor, compute: int = CTR_F32,
+                            dZ: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    lib = load()
+    B, F, d = Z.shape
+    if dZ is None:
+        dZ = torch.empty_like(Z)
+    _check("ctr_dot_interaction_bwd", lib.ctr_dot_interaction_bwd(
+        _ptr(Z), _ptr(dR), dR.stride(0), B, F, d, compute, _ptr(dZ), _stream(stream)))
+    return dZ
+
+
+def ctr_init_table_hash(table: torch.Tensor, rows: Sequence[int], seed: int, stream=None) -> None:
+    lib = load()
+    rb = (ctypes.c_int64 * (len(rows) + 1))()
+    acc = 0
+    for t, r in enumerate(rows):
+        rb[t] = acc
+        acc += int(r)
+    rb[len(rows)] = acc
+    _check("ctr_init_table_hash", lib.ctr_init_table_hash(
+        _ptr(table), _dtype_code(table), table.shape[1], ctypes.cast(rb, ctypes.c_void_p),
+        len(rows), ctypes.c_uint64(seed & 0xFFFFFFFFFFFFFFFF), _stream(stream)))
+
+
+def ctr_validate_csr(indices: torch.Tensor, offsets: torch.Tensor, batch: int, num_tables: int,
+                     bad_count: torch.Tensor, row_base: Optional[torch.Tensor] = None,
+                     total_rows: int = 0, stream=None) -> None:
+    lib = load()
+    _check("ctr_validate_csr", lib.ctr_validate_csr(
+        _ptr(indices), _index_code(indices), indices.numel(), _ptr(offsets), batch, num_tables,
+        _ptr(row_base), total_rows, _ptr(bad_count), _stream(stream)))

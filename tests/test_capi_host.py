@@ -1,0 +1,153 @@
+"""Host-side tests of the C ABI: the library loads, exports every function that
+include/ctr.h declares, and rejects bad arguments with the documented status before any
+HIP call (so these run without a GPU).  No compute call is made."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from sparse_embedding_lookup_amd import ctr
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ctr.h")
+
+
+def _lib():
+    if not os.path.exists(ctr.LIB_PATH):
+        from sparse_embedding_lookup_amd import build
+        build.build()
+    return ctr.load()
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(ctr_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_header_declares_expected_entry_points():
+    names = _declared()
+    for want in ["ctr_unique_ids", "ctr_gather_rows", "ctr_embbag_fwd", "ctr_embbag_bwd",
+                 "ctr_sparse_sgd", "ctr_dot_interaction_fwd", "ctr_dot_interaction_bwd"]:
+        assert want in names
+
+
+def test_library_exports_every_declared_symbol():
+    _lib()
+    out = subprocess.run(["nm", "-D", "--defined-only", ctr.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT\s+(ctr_\w+)", out))
+    missing = [n for n in _declared() if n not in exported]
+    assert not missing, missing
+    assert set(ctr.EXPORTED) == set(_declared())
+
+
+FAKE = ctypes.c_void_p(0x10000)       # never dereferenced: every call below fails validation
+MISALIGNED = ctypes.c_void_p(0x10004)
+
+
+def test_status_strings_and_version():
+    lib = _lib()
+    assert lib.ctr_version() >= 100
+    assert lib.ctr_status_string(0) == b"CTR_OK"
+    assert lib.ctr_status_string(3) == b"CTR_ERR_WORKSPACE_TOO_SMALL"
+
+
+def test_unique_workspace_query_and_bad_args():
+    lib = _lib()
+    wsb = ctypes.c_size_t(0)
+    assert lib.ctr_unique_ids(None, 1, 1000, None, 0, 0, None, 0, 0, None, None, None, None,
+                              None, None, ctypes.byref(wsb), None) == ctr.CTR_OK
+    assert wsb.value >= 1000 * 24
+    bad = ctypes.c_size_t(10)
+    st = lib.ctr_unique_ids(FAKE, 1, 1000, None, 0, 0, None, 0, 0, FAKE, FAKE, FAKE, None, None,
+                            FAKE, ctypes.byref(bad), None)
+    assert st == ctr.CTR_ERR_WORKSPACE_TOO_SMALL
+    assert lib.ctr_unique_ids(FAKE, 1, -1, None, 0, 0, None, 0, 0, None, None, None, None, None,
+                              None, ctypes.byref(wsb), None) == ctr.CTR_ERR_INVALID_ARGUMENT
+    assert lib.ctr_unique_ids(FAKE, 1, 2 ** 31, None, 0, 0, None, 0, 0, None, None, None, None,
+                              None, None, ctypes.byref(wsb), None) == ctr.CTR_ERR_INVALID_ARGUMENT
+    assert lib.ctr_unique_ids(FAKE, 7, 10, None, 0, 0, None, 0, 0, None, None, None, None, None,
+                              None, ctypes.byref(wsb), None) == ctr.CTR_ERR_INVALID_ARGUMENT
+    # row_base without offsets
+    assert lib.ctr_unique_ids(FAKE, 1, 10, None, 4, 2, FAKE, 100, 0, None, None, None, None, None,
+                              None, ctypes.byref(wsb), None) == ctr.CTR_ERR_INVALID_ARGUMENT
+    assert b"offsets" in lib.ctr_last_error()
+
+
+def test_embbag_fwd_bad_args():
+    lib = _lib()
+    ok = dict(table=FAKE, dtype=0, rows=100, dim=16, rb=None, T=1, idx=FAKE, it=1, nnz=10,
+              off=FAKE, B=10, out=FAKE, sb=16, st=0)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return lib.ctr_embbag_fwd(a["table"], a["dtype"], a["rows"], a["dim"], a["rb"], a["T"],
+                                  a["idx"], a["it"], a["nnz"], a["off"], a["B"], a["out"],
+                                  a["sb"], a["st"], None)
+
+    assert call(table=None) == ctr.CTR_ERR_INVALID_ARGUMENT
+    assert call(dtype=5) == ctr.CTR_ERR_INVALID_ARGUMENT
+    assert call(dim=6) == ctr.CTR_ERR_UNSUPPORTED              # not a 16-byte multiple (fp32)
+    assert call(dtype=1, dim=12) == ctr.CTR_ERR_UNSUPPORTED    # bf16 needs multiples of 8
+    assert call(table=MISALIGNED) == ctr.CTR_ERR_UNSUPPORTED
+    assert call(out=MISALIGNED) == ctr.CTR_ERR_UNSUPPORTED
+    assert call(sb=18) == ctr.CTR_ERR_UNSUPPORTED
+    assert call(it=3) == ctr.CTR_ERR_INVALID_ARGUMENT
+    assert call(nnz=-1) == ctr.CTR_ERR_INVALID_ARGUMENT
+    assert call(off=None) == ctr.CTR_ERR_INVALID_ARGUMENT
+    assert call(T=0) == ctr.CTR_ERR_INVALID_ARGUMENT
+    assert call(dim=2048) == ctr.CTR_ERR_UNSUPPORTED
+
+
+def test_embbag_bwd_workspace_and_bad_args():
+    lib = _lib()
+    wsb = ctypes.c_size_t(0)
+    assert lib.ctr_embbag_bwd(None, 64, 0, None, 10, 1, 64, 1000, None, None, None, None, None,
+                              ctypes.byref(wsb), None) == ctr.CTR_OK
+    assert wsb.value >= 1000 * 12
+    assert lib.ctr_embbag_bwd(None, 64, 0, None, 10, 1, 6, 1000, None, None, None, None, None,
+                              ctypes.byref(wsb), None) == ctr.CTR_ERR_UNSUPPORTED
+    small = ctypes.c_size_t(16)
+    assert lib.ctr_embbag_bwd(FAKE, 64, 0, FAKE, 10, 1, 64, 1000, FAKE, FAKE, FAKE, FAKE, FAKE,
+                              ctypes.byref(small), None) == ctr.CTR_ERR_WORKSPACE_TOO_SMALL
+    big = ctypes.c_size_t(wsb.value)
+    assert lib.ctr_embbag_bwd(MISALIGNED, 64, 0, FAKE, 10, 1, 64, 1000, FAKE, FAKE, FAKE, FAKE,
+                              FAKE, ctypes.byref(big), None) == ctr.CTR_ERR_UNSUPPORTED
+
+
+def test_interaction_bad_args():
+    lib = _lib()
+    f = lib.ctr_dot_interaction_fwd
+    assert f(FAKE, 10, 1, 16, 0, FAKE, 100, None) == ctr.CTR_ERR_INVALID_ARGUMENT    # F < 2
+    assert f(FAKE, 10, 5, 16, 0, FAKE, 20, None) == ctr.CTR_ERR_INVALID_ARGUMENT     # stride
+    assert f(FAKE, 10, 5, 16, 9, FAKE, 26, None) == ctr.CTR_ERR_INVALID_ARGUMENT     # compute
+    assert f(FAKE, 10, 5, 24, 1, FAKE, 40, None) == ctr.CTR_ERR_UNSUPPORTED          # bf16 dim
+    assert f(FAKE, 10, 200, 128, 1, FAKE, 30000, None) == ctr.CTR_ERR_UNSUPPORTED    # bf16 F
+    assert f(MISALIGNED, 10, 5, 16, 1, FAKE, 26, None) == ctr.CTR_ERR_UNSUPPORTED
+    b = lib.ctr_dot_interaction_bwd
+    assert b(FAKE, None, 26, 10, 5, 16, 0, FAKE, None) == ctr.CTR_ERR_INVALID_ARGUMENT  # dR NULL
+
+
+def test_sgd_gather_init_validate_bad_args():
+    lib = _lib()
+    assert lib.ctr_sparse_sgd(FAKE, 0, 100, 16, FAKE, FAKE, 10, FAKE,
+                              ctypes.c_float(float("nan")), None) == ctr.CTR_ERR_INVALID_ARGUMENT
+    assert lib.ctr_sparse_sgd(FAKE, 0, 100, 16, FAKE, FAKE, 10, MISALIGNED,
+                              ctypes.c_float(0.01), None) == ctr.CTR_ERR_UNSUPPORTED
+    assert lib.ctr_gather_rows(FAKE, 0, 100, 16, None, FAKE, 10, FAKE, None) == \
+        ctr.CTR_ERR_INVALID_ARGUMENT
+    rb = (ctypes.c_int64 * 3)(0, 10, 5)                    # decreasing
+    assert lib.ctr_init_table_hash(FAKE, 0, 16, ctypes.cast(rb, ctypes.c_void_p), 2,
+                                   ctypes.c_uint64(1), None) == ctr.CTR_ERR_INVALID_ARGUMENT
+    assert lib.ctr_validate_csr(FAKE, 1, 10, None, 10, 1, None, 100, FAKE, None) == \
+        ctr.CTR_ERR_INVALID_ARGUMENT
+
+
+def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
+    monkeypatch.setattr(ctr, "LIB_PATH", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(ctr, "_lib", None)
+    with pytest.raises(RuntimeError):
+        ctr.load()

@@ -1,0 +1,434 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle, on seeded inputs.
+
+Per-call tests give both sides identical inputs; the end-to-end tests run the whole step on
+both sides from the same workload.  Integer and index outputs must match bit for bit; floats
+within rtol * M (tests/parity.py).  Sizes span several tiles, chunks and a ragged tail.
+"""
+import sys
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import oracle as orc
+from sparse_embedding_lookup_amd import ctr, workloads
+from sparse_embedding_lookup_amd.pipeline import FrontEnd
+from tests.parity import RTOL_BF16, RTOL_F32, assert_close
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
+
+DEV = "cuda"
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+
+
+def host(t):
+    torch.cuda.synchronize()
+    return t.detach().cpu().numpy()
+
+
+def rand_csr(rng, T, B, rows, max_len, empty_frac=0.0):
+    lengths = rng.integers(1, max_len + 1, size=(T, B))
+    if empty_frac:
+        lengths[rng.random((T, B)) < empty_frac] = 0
+    off = np.zeros(T * B + 1, dtype=np.int64)
+    off[1:] = np.cumsum(lengths.reshape(-1))
+    ids = np.concatenate([rng.integers(0, rows[t], int(lengths[t].sum())) for t in range(T)])
+    return ids.astype(np.int64), off
+
+
+def gpu_table(rows, dim, dtype, seed):
+    t = torch.empty((int(sum(rows)), dim),
+                    dtype=torch.bfloat16 if dtype == "bf16" else torch.float32, device=DEV)
+    ctr.ctr_init_table_hash(t, rows, seed)
+    return t
+
+
+# ----------------------------------------------------------------------------- table fill
+@pytest.mark.parametrize("dtype,dim", [("f32", 16), ("bf16", 128), ("f32", 4)])
+def test_table_fill_matches_oracle_definition(dtype, dim):
+    say("table fill", dtype, dim)
+    rows = [1000, 37, 5000]
+    t = gpu_table(rows, dim, dtype, 77)
+    tab = orc.Table(rows, dim, dtype, 77)
+    got = host(t.float())
+    want = orc.full_table(tab)
+    np.testing.assert_array_equal(got, want)
+
+
+# ----------------------------------------------------------------------------- unique
+def _unique_cases():
+    rng = np.random.default_rng(100)
+    cases = {}
+    w = workloads.tiny()
+    cases["tiny_tables"] = (w.indices, dict(offsets=w.offsets, batch=w.batch, T=w.num_tables,
+                                            rows=w.rows))
+    w = workloads.small(batch=512)
+    cases["small_tables"] = (w.indices, dict(offsets=w.offsets, batch=w.batch, T=w.num_tables,
+                                             rows=w.rows))
+    ids = workloads.unbounded_zipf_capped(rng, 1.2, 10 ** 11, 300_001)
+    cases["tensornet_mod"] = (ids, dict(modulus=20_000_000))
+    cases["raw_signed"] = (rng.integers(-2 ** 62, 2 ** 62, size=70_001), {})
+    cases["raw_small_range_negative"] = (rng.integers(-50, 50, size=10_007), {})
+    cases["n1"] = (np.array([123456789], dtype=np.int64), {})
+    cases["all_equal"] = (np.full(100_000, 42, dtype=np.int64), dict(modulus=1000))
+    cases["all_distinct"] = (rng.permutation(65_536).astype(np.int64), dict(modulus=65_536))
+    cases["extremes"] = (np.array([2 ** 63 - 1, -2 ** 63, 0, -1, 1, 2 ** 63 - 1, -2 ** 63],
+                                  dtype=np.int64), {})
+    cases["int32_ids"] = (rng.integers(-1000, 1000, size=5000).astype(np.int32), {})
+    return cases
+
+
+UNIQUE_CASES = _unique_cases()
+
+
+@pytest.mark.parametrize("name", list(UNIQUE_CASES))
+def test_unique_matches_oracle(name):
+    ids, kw = UNIQUE_CASES[name]
+    say("unique", name, ids.shape, kw.keys())
+    n = ids.size
+    if "offsets" in kw:
+        rb = np.zeros(len(kw["rows"]) + 1, dtype=np.int64)
+        rb[1:] = np.cumsum(kw["rows"])
+        keys = orc.form_keys(ids, kw["offsets"], kw["T"], kw["batch"], rb)
+        res = ctr.ctr_unique_ids(dev(ids), offsets=dev(kw["offsets"]), batch=kw["batch"],
+                                 num_tables=kw["T"], row_base=dev(rb), total_rows=int(rb[-1]))
+    else:
+        m = kw.get("modulus", 0)
+        keys = orc.form_keys(ids.astype(np.int64), np.array([0, n]), 1, 1, None, m)
+        res = ctr.ctr_unique_ids(dev(ids), key_modulus=m)
+    uniq, inv, nu, perm, seg = [host(x) for x in res]
+    U = int(nu[0])
+    ou, oi, op, os_ = orc.unique(keys)
+    assert U == ou.size
+    np.testing.assert_array_equal(uniq[:U], ou)
+    np.testing.assert_array_equal(inv, oi)
+    np.testing.assert_array_equal(perm, op)
+    np.testing.assert_array_equal(seg[:U + 1], os_)
+
+
+def test_unique_empty():
+    res = ctr.ctr_unique_ids(torch.zeros(0, dtype=torch.int64, device=DEV), key_modulus=10)
+    nu, seg = host(res[2]), host(res[4])
+    assert nu[0] == 0 and seg[0] == 0
+
+
+# ----------------------------------------------------------------------------- gather rows
+@pytest.mark.parametrize("dtype,dim", [("f32", 32), ("bf16", 128), ("f32", 4)])
+def test_gather_rows_bit_exact(dtype, dim):
+    say("gather", dtype, dim)
+    rows = [20_000]
+    t = gpu_table(rows, dim, dtype, 5)
+    tab = orc.Table(rows, dim, dtype, 5)
+    rng = np.random.default_rng(6)
+    U = 3001
+    r = rng.integers(0, rows[0], size=U)
+    cap = U + 100
+    rr = np.zeros(cap, dtype=np.int64)
+    rr[:U] = r
+    out = ctr.ctr_gather_rows(t, dev(rr), dev(np.array([U], np.int32)), cap)
+    got = host(out)[:U]
+    np.testing.assert_array_equal(got, orc.gather_rows(tab, r))
+
+
+# ----------------------------------------------------------------------------- pooling
+def _fwd_case(name):
+    rng = np.random.default_rng(zlib.crc32(name.encode()))
+    if name == "tiny":
+        w = workloads.tiny()
+        return w.rows, w.dim, w.dtype, w.indices, w.offsets, w.batch, w.num_tables
+    if name == "small_b512":
+        w = workloads.small(batch=512)
+        return w.rows, w.dim, w.dtype, w.indices, w.offsets, w.batch, w.num_tables
+    if name == "criteo_b512":
+        w = workloads.criteo(batch=512)
+        return w.rows, w.dim, w.dtype, w.indices, w.offsets, w.batch, w.num_tables
+    if name == "empty_bags_d4":
+        rows = [100, 300]
+        ids, off = rand_csr(rng, 2, 333, rows, 7, empty_frac=0.3)
+        return rows, 4, "f32", ids, off, 333, 2
+    if name == "bf16_d8_long":
+        rows = [5000]
+        ids, off = rand_csr(rng, 1, 97, rows, 300)
+        return rows, 8, "bf16", ids, off, 97, 1
+    if name == "f32_d512":
+        rows = [2000, 2000]
+        ids, off = rand_csr(rng, 2, 100, rows, 20)
+        return rows, 512, "f32", ids, off, 100, 2
+    if name == "one_bag_200k":
+        rows = [100_000]
+        off = np.array([0, 200_000], dtype=np.int64)
+        ids = rng.integers(0, rows[0], size=200_000)
+        return rows, 16, "f32", ids, off, 1, 1
+    raise KeyError(name)
+
+
+FWD_CASES = ["tiny", "small_b512", "criteo_b512", "empty_bags_d4", "bf16_d8_long", "f32_d512",
+             "one_bag_200k"]
+
+
+@pytest.mark.parametrize("name", FWD_CASES)
+@pytest.mark.parametrize("itype", ["i64", "i32"])
+def test_embbag_fwd_matches_oracle(name, itype):
+    rows, dim, dtype, ids, off, B, T = _fwd_case(name)
+    say("embbag_fwd", name, itype, len(ids))
+    t = gpu_table(rows, dim, dtype, 11)
+    tab = orc.Table(rows, dim, dtype, 11)
+    rb = tab.row_base
+    out = torch.full((B, T, dim), float("nan"), dtype=torch.float32, device=DEV)
+    gi = dev(ids.astype(np.int32 if itype == "i32" else np.int64))
+    ctr.ctr_embbag_fwd(t, gi, dev(off), B, T, out, T * dim, dim, row_base=dev(rb))
+    got = host(out)
+    want, mag = orc.embbag_fwd(tab, ids, off, B)
+    assert_close(got, want, mag, RTOL_F32, "embbag_fwd " + name)
+    # bags of one occurrence are exact row copies, empty bags exact zeros
+    lens = np.diff(off).reshape(T, B).T
+    single = lens <= 1
+    np.testing.assert_array_equal(got[single], want[single])
+
+
+# ----------------------------------------------------------------------------- interaction
+INTER_CASES = [
+    ("f32", 128, 5, 16), ("f32", 2048, 9, 64), ("f32", 77, 2, 4), ("f32", 33, 27, 128),
+    ("bf16", 100, 27, 128), ("bf16", 67, 65, 128), ("bf16", 40, 5, 16), ("bf16", 9, 2, 32),
+    ("bf16", 13, 100, 64), ("f32", 5, 65, 128),
+]
+
+
+def _inter_inputs(B, F, d, seed):
+    rng = np.random.default_rng(seed)
+    Z = rng.standard_normal((B, F, d)).astype(np.float32)
+    dR = rng.standard_normal((B, d + F * (F - 1) // 2)).astype(np.float32)
+    return Z, dR
+
+
+@pytest.mark.parametrize("compute,B,F,d", INTER_CASES)
+def test_interaction_fwd_matches_oracle(compute, B, F, d):
+    say("interaction_fwd", compute, B, F, d)
+    Z, _ = _inter_inputs(B, F, d, 1)
+    code = ctr.CTR_BF16 if compute == "bf16" else ctr.CTR_F32
+    R = host(ctr.ctr_dot_interaction_fwd(dev(Z), code))
+    want, mag = orc.interaction_fwd(Z.astype(np.float64))
+    assert_close(R, want, mag, RTOL_BF16 if compute == "bf16" else RTOL_F32, "interaction_fwd")
+    np.testing.assert_array_equal(R[:, :d], Z[:, 0, :])
+
+
+@pytest.mark.parametrize("compute,B,F,d", INTER_CASES)
+def test_interaction_bwd_matches_oracle(compute, B, F, d):
+    say("interaction_bwd", compute, B, F, d)
+    Z, dR = _inter_inputs(B, F, d, 2)
+    code = ctr.CTR_BF16 if compute == "bf16" else ctr.CTR_F32
+    dZ = host(ctr.ctr_dot_interaction_bwd(dev(Z), dev(dR), code))
+    want, mag = orc.interaction_bwd(Z.astype(np.float64), dR.astype(np.float64))
+    assert_close(dZ, want, mag, RTOL_BF16 if compute == "bf16" else RTOL_F32, "interaction_bwd")
+
+
+def test_interaction_strided_output():
+    B, F, d = 50, 9, 64
+    Z, dR = _inter_inputs(B, F, d, 3)
+    P = F * (F - 1) // 2
+    big = torch.full((B, d + P + 12), -7.0, device=DEV)
+    ctr.ctr_dot_interaction_fwd(dev(Z), ctr.CTR_F32, big)
+    got = host(big)
+    want, mag = orc.interaction_fwd(Z.astype(np.float64))
+    assert_close(got[:, :d + P], want, mag, RTOL_F32, "strided R")
+    assert np.all(got[:, d + P:] == -7.0)
+
+
+# ----------------------------------------------------------------------------- backward
+def _bwd_case(name):
+    rng = np.random.default_rng(zlib.crc32(name.encode()) + 1)
+    if name == "tiny":
+        w = workloads.tiny()
+        return w.rows, w.dim, w.indices, w.offsets, w.batch, w.num_tables
+    if name == "small_b512":
+        w = workloads.small(batch=512)
+        return w.rows, w.dim, w.indices, w.offsets, w.batch, w.num_tables
+    if name == "criteo_b256":
+        w = workloads.criteo(batch=256)
+        return w.rows, w.dim, w.indices, w.offsets, w.batch, w.num_tables
+    if name == "hot_segment_d32":
+        # one key holds ~40% of 300k occurrences: long segment across many chunks and levels
+        rows = [1000]
+        B = 300_000
+        ids = np.where(rng.random(B) < 0.4, 7, rng.integers(0, 1000, B)).astype(np.int64)
+        off = np.arange(B + 1, dtype=np.int64)
+        return rows, 32, ids, off, B, 1
+    if name == "all_one_key_d16":
+        rows = [10]
+        B = 150_001
+        return rows, 16, np.full(B, 3, np.int64), np.arange(B + 1, dtype=np.int64), B, 1
+    if name == "empty_bags_d4":
+        rows = [50, 70]
+        ids, off = rand_csr(rng, 2, 401, rows, 9, empty_frac=0.25)
+        return rows, 4, ids, off, 401, 2
+    if name == "d512":
+        rows = [300, 300]
+        ids, off = rand_csr(rng, 2, 120, rows, 30)
+        return rows, 512, ids, off, 120, 2
+    raise KeyError(name)
+
+
+BWD_CASES = ["tiny", "small_b512", "criteo_b256", "hot_segment_d32", "all_one_key_d16",
+             "empty_bags_d4", "d512"]
+
+
+@pytest.mark.parametrize("name", BWD_CASES)
+def test_embbag_bwd_matches_oracle(name):
+    rows, dim, ids, off, B, T = _bwd_case(name)
+    say("embbag_bwd", name, len(ids))
+    rng = np.random.default_rng(9)
+    # gradient laid out like dZ[:, 1:, :] of a [B, T+1, dim] buffer
+    dZ = rng.standard_normal((B, T + 1, dim)).astype(np.float32)
+    rb = np.zeros(T + 1, dtype=np.int64)
+    rb[1:] = np.cumsum(rows)
+    keys = orc.form_keys(ids, off, T, B, rb)
+    uniq, inv, perm, seg = orc.unique(keys)
+    U = uniq.size
+    g_dev = dev(dZ)
+    rg = ctr.ctr_embbag_bwd(g_dev[:, 1:, :], (T + 1) * dim, dim, dev(off), B, T, dim,
+                            dev(perm), dev(inv), dev(np.array([U], np.int32)))
+    got = host(rg)[:U]
+    want, mag = orc.embbag_bwd(dZ[:, 1:, :].astype(np.float64), off, B, T, inv, U)
+    assert_close(got, want, mag, RTOL_F32, "embbag_bwd " + name)
+
+
+# ----------------------------------------------------------------------------- SGD
+@pytest.mark.parametrize("dtype,dim", [("f32", 64), ("bf16", 128), ("f32", 4)])
+def test_sparse_sgd_matches_oracle(dtype, dim):
+    say("sgd", dtype, dim)
+    rows = [4000, 3000]
+    t = gpu_table(rows, dim, dtype, 21)
+    before = host(t.float())
+    tab = orc.Table(rows, dim, dtype, 21)
+    rng = np.random.default_rng(22)
+    U = 1500
+    uniq = np.sort(rng.choice(7000, size=U, replace=False)).astype(np.int64)
+    g = rng.standard_normal((U, dim)).astype(np.float32)
+    cap = U + 64
+    uq = np.zeros(cap, np.int64)
+    uq[:U] = uniq
+    gg = np.zeros((cap, dim), np.float32)
+    gg[:U] = g
+    ctr.ctr_sparse_sgd(t, dev(uq), dev(np.array([U], np.int32)), cap, dev(gg), 0.01)
+    after = host(t.float())
+    want, mag = orc.sparse_sgd(tab, uniq, g.astype(np.float64), np.abs(g).astype(np.float64), 0.01)
+    assert_close(after[uniq], want, mag, RTOL_BF16 if dtype == "bf16" else RTOL_F32, "sgd rows")
+    untouched = np.ones(7000, bool)
+    untouched[uniq] = False
+    np.testing.assert_array_equal(after[untouched], before[untouched])
+
+
+def test_sparse_sgd_lr_zero_is_identity():
+    rows = [500]
+    t = gpu_table(rows, 16, "bf16", 3)
+    before = host(t.float())
+    U = 100
+    uq = np.arange(U, dtype=np.int64) * 5
+    g = np.random.default_rng(1).standard_normal((U, 16)).astype(np.float32)
+    ctr.ctr_sparse_sgd(t, dev(uq), dev(np.array([U], np.int32)), U, dev(g), 0.0)
+    np.testing.assert_array_equal(host(t.float()), before)
+
+
+# ----------------------------------------------------------------------------- end to end
+def _oracle_dlrm_step(w):
+    tab = orc.Table(w.rows, w.dim, w.dtype, w.table_seed)
+    pooled, pmag = orc.embbag_fwd(tab, w.indices, w.offsets, w.batch)
+    B, F, d = w.batch, w.F, w.dim
+    Z = np.empty((B, F, d))
+    Zm = np.empty((B, F, d))
+    Z[:, 0] = w.dense
+    Zm[:, 0] = np.abs(w.dense)
+    Z[:, 1:] = pooled
+    Zm[:, 1:] = pmag
+    R, Rm = orc.interaction_fwd(Z, Zm)
+    dZ, dZm = orc.interaction_bwd(Z, w.grad_out.astype(np.float64), Zm)
+    keys = orc.form_keys(w.indices, w.offsets, w.num_tables, B, w.row_base)
+    uniq, inv, perm, seg = orc.unique(keys)
+    g, gm = orc.embbag_bwd(dZ[:, 1:], w.offsets, B, w.num_tables, inv, uniq.size, dZm[:, 1:])
+    new, nm = orc.sparse_sgd(tab, uniq, g, gm, w.lr)
+    return dict(Z=Z, Zm=Zm, R=R, Rm=Rm, dZ=dZ, dZm=dZm, uniq=uniq, inv=inv, perm=perm, g=g,
+                gm=gm, new=new, nm=nm)
+
+
+@pytest.mark.parametrize("name", ["tiny", "small_b256", "criteo_b128"])
+def test_end_to_end_dlrm_step(name):
+    w = {"tiny": workloads.tiny, "small_b256": lambda: workloads.small(batch=256),
+         "criteo_b128": lambda: workloads.criteo(batch=128)}[name]()
+    say("end_to_end", name, w.nnz)
+    fe = FrontEnd(w, DEV)
+    fe.step()
+    o = _oracle_dlrm_step(w)
+    rt = RTOL_BF16 if w.compute == "bf16" else RTOL_F32
+    # chained tolerances: magnitudes propagate through the chain, a few roundings per stage
+    assert_close(host(fe.Z), o["Z"], o["Zm"], RTOL_F32, "Z")
+    assert_close(host(fe.R), o["R"], o["Rm"], 3 * rt, "R")
+    assert_close(host(fe.dZ), o["dZ"], o["dZm"], 3 * rt, "dZ")
+    U = int(host(fe.num_unique)[0])
+    assert U == o["uniq"].size
+    np.testing.assert_array_equal(host(fe.uniq)[:U], o["uniq"])
+    np.testing.assert_array_equal(host(fe.inverse), o["inv"])
+    assert_close(host(fe.row_grads)[:U], o["g"], o["gm"], 4 * rt, "row grads")
+    tbl = host(fe.table[dev(o["uniq"])].float())
+    # the update inherits the chained gradient error (4 rt) plus one storage rounding
+    assert_close(tbl, o["new"], o["nm"], 4 * rt + (RTOL_BF16 if w.dtype == "bf16" else 0.0),
+                 "updated rows")
+
+
+def test_end_to_end_tensornet_step_reduced():
+    w = workloads.tensornet(batch=2048, slots=100)
+    say("end_to_end tensornet", w.nnz)
+    fe = FrontEnd(w, DEV)
+    fe.step()
+    tab = orc.Table(w.rows, w.dim, w.dtype, w.table_seed)
+    keys = orc.form_keys(w.indices, w.offsets, 1, w.nnz, np.array([0, w.rows[0]]), w.key_modulus)
+    uniq, inv, perm, seg = orc.unique(keys)
+    U = uniq.size
+    assert int(host(fe.num_unique)[0]) == U
+    np.testing.assert_array_equal(host(fe.uniq)[:U], uniq)
+    np.testing.assert_array_equal(host(fe.inverse), inv)
+    # batch-sized matrix and per-slot vectors are exact copies of table rows
+    E = orc.gather_rows(tab, uniq)
+    np.testing.assert_array_equal(host(fe.E)[:U], E)
+    np.testing.assert_array_equal(host(fe.out), E[inv])
+    dout = w.grad_out.reshape(w.nnz, 1, w.dim).astype(np.float64)
+    g, gm = orc.embbag_bwd(dout, w.offsets, w.nnz, 1, inv, U)
+    assert_close(host(fe.row_grads)[:U], g, gm, RTOL_F32, "tensornet row grads")
+    new, nm = orc.sparse_sgd(tab, uniq, g, gm, w.lr)
+    assert_close(host(fe.table[dev(uniq)]), new, nm, 2 * RTOL_F32, "tensornet rows")
+
+
+def test_step_is_deterministic():
+    w = workloads.small(batch=256)
+    outs = []
+    for _ in range(2):
+        fe = FrontEnd(w, DEV)
+        fe.step()
+        U = int(host(fe.num_unique)[0])
+        outs.append((host(fe.R).copy(), host(fe.dZ).copy(), host(fe.row_grads)[:U].copy(),
+                     host(fe.table[:100_000]).copy()))
+    for a, b in zip(*outs):
+        np.testing.assert_array_equal(a, b)
+
+
+def test_validate_csr_counts_violations():
+    rows = [10, 20]
+    rb = dev(np.array([0, 10, 30], np.int64))
+    off = np.array([0, 2, 4, 5, 7], np.int64)          # T=2, B=2
+    ids = np.array([1, 9, 10, 3, 19, 20, -1], np.int64)  # 10 (t0), 20 and -1 (t1) are bad
+    bad = torch.zeros(1, dtype=torch.int32, device=DEV)
+    ctr.ctr_validate_csr(dev(ids), dev(off), 2, 2, bad, row_base=rb)
+    assert int(host(bad)[0]) == 3
+    bad.zero_()
+    ctr.ctr_validate_csr(dev(np.array([0, 1, 2], np.int64)), dev(np.array([0, 2, 1, 3], np.int64)),
+                         3, 1, bad, total_rows=5)
+    assert int(host(bad)[0]) == 1                          # offsets decrease once
