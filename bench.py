@@ -1,0 +1,233 @@
+#!/usr/bin/env python3
+"""Benchmark of the sparse front end of a CTR ranking model on one MI355X.
+
+A step is one pass of the whole path over one batch of seeded synthetic input, with inputs
+already resident in HBM:
+  DLRM-shaped workloads:  embbag_fwd -> interaction_fwd -> interaction_bwd -> unique ->
+                          embbag_bwd -> sparse_sgd
+  TensorNet workload:     unique -> gather_rows -> embbag_fwd (per-slot) -> embbag_bwd ->
+                          sparse_sgd
+Prints one JSON line: rows gathered per second over whole steps (value), HBM GB/s of the
+algorithmic bytes, interaction samples/s, the roofline of the dominant kernel (timed with
+HIP events on its stream inside the timed region) and the CPU oracle timed on a bounded
+sample of the same workload.
+
+    python bench.py [--config small|tiny|criteo|tensornet|large] [--steps K] [--warmup W]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0      # MI355X HBM3E, published
+WORKLOAD_NAMES = {
+    "tiny": "Tiny: 4 fp32 tables x 1000 x d16, B=128, one-hot, F=5",
+    "small": "Small DLRM-shaped: 8 fp32 tables x 1M x d64, B=2048, Poisson(20) bags, Zipf(1.05), F=9",
+    "criteo": "Criteo-shaped: 26 bf16 tables (1e3..1e7 rows) x d128, B=8192, F=27",
+    "tensornet": "TensorNet batch-unique: 65536 x 100 IDs, Zipf(1.2) over 1e11, mod 2e7, fp32 d32",
+    "large": "Large: 64 bf16 tables x 4M x d128, B=32768, Poisson(32) bags, Zipf(1.1), F=65",
+}
+
+
+def stage_bytes(w, U):
+    """Algorithmic bytes moved by each stage (what the method must read and write)."""
+    n = w.nnz
+    d = w.dim
+    rb = d * (2 if w.dtype == "bf16" else 4)
+    if w.interaction:
+        B, T, F, P = w.batch, w.num_tables, w.F, w.P
+        nb = T * B
+        return {
+            "embbag_fwd": n * rb + 8 * n + 8 * (nb + 1) + 4 * nb * d,
+            "interaction_fwd": 4 * B * F * d + 4 * B * (d + P),
+            "interaction_bwd": 4 * B * (d + P) + 8 * B * F * d,
+            "unique": 8 * n + 8 * (nb + 1) + 4 * n + 4 * n + 12 * U + 4 * U,
+            "embbag_bwd": 4 * n * d + 4 * n + 4 * n + 8 * (nb + 1) + 4 * U * d,
+            "sparse_sgd": 2 * U * rb + 4 * U * d + 8 * U,
+        }
+    return {
+        "unique": 8 * n + 4 * n + 4 * n + 12 * U + 4 * U,
+        "gather_rows": U * rb + 8 * U + 4 * U * d,
+        "embbag_fwd": n * 4 * d + 4 * n + 8 * (n + 1) + 4 * n * d,
+        "embbag_bwd": 4 * n * d + 4 * n + 4 * n + 8 * (n + 1) + 4 * U * d,
+        "sparse_sgd": 2 * U * rb + 4 * U * d + 8 * U,
+    }
+
+
+# Stages that are one kernel launch each (a roofline needs one kernel's duration).
+SINGLE_KERNEL = {"embbag_fwd", "interaction_fwd", "interaction_bwd", "sparse_sgd", "gather_rows"}
+
+
+def cpu_baseline(w, seconds: float):
+    """The oracle, as it stands, on repeated full batches until `seconds` of CPU time."""
+    import numpy as np
+    from oracle import oracle as orc
+
+    threads = orc.get_threads()
+    tab = orc.Table(w.rows, w.dim, w.dtype, w.table_seed)
+    if w.total_rows * w.dim * 4 <= (4 << 30):
+        tab = orc.Table(w.rows, w.dim, w.dtype, w.table_seed, data=orc.full_table(tab))
+        sample_tab = "host copy of the tables"
+    else:
+        sample_tab = "rows regenerated from the counter-based fill"
+
+    def one_step():
+        if w.interaction:
+            pooled, _ = orc.embbag_fwd(tab, w.indices, w.offsets, w.batch)
+            Z = np.empty((w.batch, w.F, w.dim))
+            Z[:, 0] = w.dense
+            Z[:, 1:] = pooled
+            orc.interaction_fwd(Z)
+            dZ, _ = orc.interaction_bwd(Z, w.grad_out)
+            keys = orc.form_keys(w.indices, w.offsets, w.num_tables, w.batch, w.row_base)
+            uniq, inv, _, _ = orc.unique(keys)
+            g, gm = orc.embbag_bwd(dZ[:, 1:], w.offsets, w.batch, w.num_tables, inv, uniq.size)
+            orc.sparse_sgd(tab, uniq, g, gm, w.lr)
+        else:
+            keys = orc.form_keys(w.indices, w.offsets, 1, w.nnz, np.array([0, w.rows[0]]),
+                                 w.key_modulus)
+            uniq, inv, _, _ = orc.unique(keys)
+            E = orc.gather_rows(tab, uniq)
+            Et = orc.Table([uniq.size], w.dim, "f32", 0, data=E.astype(np.float32))
+            orc.embbag_fwd(Et, inv.astype(np.int64), w.offsets, w.nnz)
+            g, gm = orc.embbag_bwd(w.grad_out.reshape(w.nnz, 1, w.dim), w.offsets, w.nnz, 1,
+                                   inv, uniq.size)
+            orc.sparse_sgd(tab, uniq, g, gm, w.lr)
+
+    reps = 0
+    t0 = time.perf_counter()
+    while True:
+        one_step()
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds or reps >= 1000:
+            break
+    return {"value": reps * w.nnz / el, "unit": "rows/s", "cores": threads, "kind": "oracle",
+            "sample": "%d full oracle step(s) of the same batch (%d rows each, %s) in %.1f s"
+                      % (reps, w.nnz, sample_tab, el),
+            "seconds_per_step": el / reps}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="small", choices=sorted(WORKLOAD_NAMES))
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--detail", default="", help="write per-stage detail JSON here")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(--gpus %d requested)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from sparse_embedding_lookup_amd import ctr, workloads
+    from sparse_embedding_lookup_amd.pipeline import FrontEnd
+
+    ctr.load()
+    print("[bench] generating workload %s" % args.config, file=sys.stderr, flush=True)
+    w = workloads.make(args.config)
+    print("[bench] nnz=%d, building device state" % w.nnz, file=sys.stderr, flush=True)
+    fe = FrontEnd(w, "cuda")
+    st = fe.stages()
+    torch.cuda.synchronize()
+
+    for _ in range(args.warmup):
+        fe.step()
+    torch.cuda.synchronize()
+    U = int(fe.num_unique.cpu()[0])
+
+    # Per-stage durations from HIP events (diagnostic pass, not the timed region).
+    K = args.steps
+    evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            for _ in st] for _ in range(K)]
+    for k in range(K):
+        for (name, fn), (e0, e1) in zip(st, evs[k]):
+            e0.record()
+            fn()
+            e1.record()
+    torch.cuda.synchronize()
+    stage_ms = {name: sum(evs[k][i][0].elapsed_time(evs[k][i][1]) for k in range(K)) / K
+                for i, (name, _) in enumerate(st)}
+    byts = stage_bytes(w, U)
+    dominant = max((s for s in stage_ms if s in SINGLE_KERNEL), key=lambda s: stage_ms[s])
+
+    # Timed region: K whole steps as the pipeline runs them (unique on a second stream for
+    # the DLRM-shaped step); events bracket the dominant kernel on the stream it runs on.
+    print("[bench] timing %d steps" % K, file=sys.stderr, flush=True)
+    dev0 = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    dev1 = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    cur = [0]
+
+    def mark(name, fn):
+        if name == dominant:
+            dev0[cur[0]].record()
+            fn()
+            dev1[cur[0]].record()
+        else:
+            fn()
+
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(K):
+        cur[0] = k
+        fe.step(mark)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_step = (t1 - t0) * 1e3 / K
+    dom_ms = sum(dev0[k].elapsed_time(dev1[k]) for k in range(K)) / K
+
+    step_bytes = sum(byts.values())
+    value = w.nnz / (ms_step * 1e-3)
+    achieved = byts[dominant] / (dom_ms * 1e-3) / 1e9
+    out = {
+        "metric": "embedding rows gathered/s + HBM GB/s (fwd+bwd); interaction samples/s",
+        "value": value,
+        "unit": "rows/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "data": "synthetic (seeded; tables from the counter-based fill)",
+        "config": {"workload": WORKLOAD_NAMES[args.config], "name": args.config,
+                   "batch": w.batch, "tables": w.num_tables, "dim": w.dim, "nnz": w.nnz,
+                   "unique_rows": U},
+        "hbm_gbps_algorithmic": step_bytes / (ms_step * 1e-3) / 1e9,
+        "interaction_samples_per_s": (w.batch / ((stage_ms["interaction_fwd"] +
+                                                  stage_ms["interaction_bwd"]) * 1e-3)
+                                      if w.interaction else None),
+        "stage_ms": {k: round(v, 5) for k, v in stage_ms.items()},
+        "roofline": {"kernel": dominant, "bound": "hbm", "achieved": achieved,
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
+                     "traffic": None, "bytes_per_launch": byts[dominant],
+                     "avg_launch_ms": dom_ms},
+    }
+    if not args.no_cpu:
+        print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
+        cb = cpu_baseline(w, args.cpu_seconds)
+        out["cpu_baseline"] = {k: cb[k] for k in ("value", "unit", "cores", "kind", "sample")}
+    if args.detail:
+        det = dict(out)
+        det["stage_bytes"] = byts
+        det["stage_gbps"] = {k: byts[k] / (stage_ms[k] * 1e-3) / 1e9 for k in stage_ms}
+        with open(args.detail, "w") as f:
+            json.dump(det, f, indent=1)
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

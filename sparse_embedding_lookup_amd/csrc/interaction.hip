@@ -250,12 +250,16 @@ __global__ __launch_bounds__(kThreads) void interaction_bwd_mfma_kernel(
   }
 }
 
-int f32_spb(int F, int dim, bool bwd) {
+// Samples per block of the fp32 kernels: as many as 32 KiB of LDS holds, but no more than
+// keeps about 1024 blocks in flight (four per CU), so small batches still fill the chip.
+int f32_spb(int64_t batch, int F, int dim, bool bwd) {
   const int per = (F * (dim + 1) + (bwd ? F * (F - 1) / 2 : 0)) * 4;
-  int spb = 32768 / per;
+  int64_t spb = 32768 / per;
+  const int64_t fill = batch / 1024;
+  if (spb > fill) spb = fill;
   if (spb < 1) spb = 1;
   if (spb > 64) spb = 64;
-  return spb;
+  return (int)spb;
 }
 
 }  // namespace
@@ -286,7 +290,7 @@ hipError_t launch_interaction_fwd(const float* Z, int64_t batch, int F, int dim,
                                   float* R, int64_t r_stride, hipStream_t s) {
   if (batch == 0) return hipSuccess;
   if (!bf16) {
-    const int spb = f32_spb(F, dim, false);
+    const int spb = f32_spb(batch, F, dim, false);
     const size_t lds = (size_t)spb * F * (dim + 1) * sizeof(float);
     const int64_t blocks = (batch + spb - 1) / spb;
     interaction_fwd_f32_kernel<<<(unsigned)blocks, kThreads, lds, s>>>(Z, batch, F, dim, spb, R,
@@ -312,7 +316,7 @@ hipError_t launch_interaction_bwd(const float* Z, const float* dR, int64_t dr_st
   if (batch == 0) return hipSuccess;
   const int P = F * (F - 1) / 2;
   if (!bf16) {
-    const int spb = f32_spb(F, dim, true);
+    const int spb = f32_spb(batch, F, dim, true);
     const size_t lds = (size_t)spb * (F * (dim + 1) + P) * sizeof(float);
     const int64_t blocks = (batch + spb - 1) / spb;
     interaction_bwd_f32_kernel<<<(unsigned)blocks, kThreads, lds, s>>>(Z, dR, dr_stride, batch,

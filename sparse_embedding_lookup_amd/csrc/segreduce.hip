@@ -21,8 +21,7 @@ namespace ctr {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kPerSlot = 64;     // positions summed serially by one slot
-constexpr int kUnroll = 8;
+constexpr int kPerSlot = 16;     // positions summed serially by one slot
 
 __global__ __launch_bounds__(kThreads) void bag_of_kernel(const int64_t* __restrict__ offsets,
                                                           int64_t num_bags, int64_t nnz,
@@ -145,44 +144,66 @@ __global__ __launch_bounds__(kThreads) void segreduce_kernel(
 
   int32_t fkey = -1, fcont = 0, lkey = -1;
   if (q0 < n) {
+    // Prefetch the slot's entries cooperatively: entry e is loaded by lane e % G of the slot
+    // into register e / G, then broadcast with shuffles.
+    constexpr int kRegs = (kPerSlot + G - 1) / G;
+    const int lane0 = (threadIdx.x & 63) & ~(G - 1);
+    int32_t ekey[kRegs];
+    int32_t ebag[kRegs];
+#pragma unroll
+    for (int r = 0; r < kRegs; ++r) {
+      const int e = r * G + lane;
+      const int64_t p = q0 + e;
+      ekey[r] = -1;
+      ebag[r] = 0;
+      if (e < kPerSlot && p < q1) {
+        if constexpr (L0) {
+          const int2 sr = S.src[p];
+          ekey[r] = sr.x;
+          ebag[r] = sr.y;
+        } else {
+          ekey[r] = S.keys[p];
+        }
+      }
+    }
     const int32_t kb = key_before<L0>(S, q0);
+    const int32_t ka = key_after<L0>(S, q1, n);
     int32_t cur = -1;
     bool cur_before = false;
     bool first_seen = false;
     RowAcc<VPL> acc;
     acc.zero();
-    for (int64_t p0 = q0; p0 < q1; p0 += kUnroll) {
-      int32_t kk[kUnroll];
-      float4 rv[kUnroll][VPL];
+    constexpr int kBatch = VPL == 1 ? kPerSlot : 8;
 #pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
-        const int64_t p = p0 + u;
-        kk[u] = -1;
+    for (int b0 = 0; b0 < kPerSlot; b0 += kBatch) {
+      int32_t kk[kBatch];
+      float4 rv[kBatch][VPL];
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        const int e = b0 + u;
+        const int64_t p = q0 + e;
         const float* rp = nullptr;
-        if (p < q1) {
-          if constexpr (L0) {
-            const int2 sr = S.src[p];
-            kk[u] = sr.x;
-            int64_t bag = sr.y;
-            if (bag < 0 || bag >= S.num_bags) bag = 0;
-            const int64_t t = bag / S.batch, b = bag - t * S.batch;
-            rp = S.grad + b * S.sb + t * S.st;
-          } else {
-            kk[u] = S.keys[p];
-            rp = S.rows + p * (int64_t)S.dim;
-          }
+        kk[u] = __shfl(ekey[e / G], lane0 + (e % G), 64);
+        if constexpr (L0) {
+          int64_t bag = __shfl(ebag[e / G], lane0 + (e % G), 64);
+          if (bag < 0 || bag >= S.num_bags) bag = 0;
+          const int64_t t = bag / S.batch, b = bag - t * S.batch;
+          rp = S.grad + b * S.sb + t * S.st;
+        } else {
+          rp = S.rows + p * (int64_t)S.dim;
         }
 #pragma unroll
         for (int a = 0; a < VPL; ++a) {
           const int c = col(a);
-          if (rp && kk[u] != -1 && c < dim)
+          // carry rows load without waiting for their key (empty entries are skipped below)
+          if (p < q1 && c < dim && (!L0 || kk[u] != -1))
             rv[u][a] = *reinterpret_cast<const float4*>(rp + c);
           else
             rv[u][a] = make_float4(0.f, 0.f, 0.f, 0.f);
         }
       }
 #pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
+      for (int u = 0; u < kBatch; ++u) {
         if (kk[u] == -1) continue;
         if (kk[u] != cur) {
           if (cur != -1) {             // previous segment ended inside this slot
@@ -212,7 +233,7 @@ __global__ __launch_bounds__(kThreads) void segreduce_kernel(
       }
     }
     if (cur != -1) {
-      const bool cont = key_after<L0>(S, q1, n) == cur;
+      const bool cont = ka == cur;
       if (cur_before) {
         fkey = cur;
         fcont = cont ? 1 : 0;

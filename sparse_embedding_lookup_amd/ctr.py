@@ -106,6 +106,23 @@ def _workspace(nbytes: int, device) -> torch.Tensor:
     return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
 
 
+def unique_workspace_bytes(n: int) -> int:
+    """Workspace of ctr_unique_ids for n occurrences (the library's two-call query)."""
+    wsb = ctypes.c_size_t(0)
+    _check("ctr_unique_ids", load().ctr_unique_ids(None, CTR_I64, n, None, 0, 0, None, 0, 0,
+                                                   None, None, None, None, None, None,
+                                                   ctypes.byref(wsb), None))
+    return wsb.value
+
+
+def embbag_bwd_workspace_bytes(nnz: int, dim: int) -> int:
+    """Workspace of ctr_embbag_bwd (the library's two-call query)."""
+    wsb = ctypes.c_size_t(0)
+    _check("ctr_embbag_bwd", load().ctr_embbag_bwd(None, 0, 0, None, 1, 1, dim, nnz, None, None,
+                                                   None, None, None, ctypes.byref(wsb), None))
+    return wsb.value
+
+
 # ----------------------------------------------------------------------------- entry points
 def ctr_version() -> int:
     return int(load().ctr_version())
@@ -114,25 +131,29 @@ def ctr_version() -> int:
 def ctr_unique_ids(ids: torch.Tensor, *, offsets: Optional[torch.Tensor] = None, batch: int = 0,
                    num_tables: int = 0, row_base: Optional[torch.Tensor] = None,
                    total_rows: int = 0, key_modulus: int = 0, want_perm: bool = True,
-                   want_seg: bool = True, workspace: Optional[torch.Tensor] = None, stream=None
+                   want_seg: bool = True, workspace: Optional[torch.Tensor] = None,
+                   out: Optional[tuple] = None, stream=None
                    ) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor, Optional[torch.Tensor],
                               Optional[torch.Tensor]]:
     """Returns (uniq int64[n], inverse int32[n], num_unique int32[1], perm, seg_offsets);
-    only the first num_unique entries of uniq (and num_unique+1 of seg_offsets) are set."""
+    only the first num_unique entries of uniq (and num_unique+1 of seg_offsets) are set.
+    ``out`` may supply those five tensors (perm / seg_offsets may be None)."""
     lib = load()
     n = ids.numel()
     dev = ids.device
-    uniq = torch.empty(max(n, 1), dtype=torch.int64, device=dev)
-    inv = torch.empty(max(n, 1), dtype=torch.int32, device=dev)
-    nu = torch.empty(1, dtype=torch.int32, device=dev)
-    perm = torch.empty(max(n, 1), dtype=torch.int32, device=dev) if want_perm else None
-    seg = torch.empty(n + 1, dtype=torch.int32, device=dev) if want_seg else None
+    if out is not None:
+        uniq, inv, nu, perm, seg = out
+    else:
+        uniq = torch.empty(max(n, 1), dtype=torch.int64, device=dev)
+        inv = torch.empty(max(n, 1), dtype=torch.int32, device=dev)
+        nu = torch.empty(1, dtype=torch.int32, device=dev)
+        perm = torch.empty(max(n, 1), dtype=torch.int32, device=dev) if want_perm else None
+        seg = torch.empty(n + 1, dtype=torch.int32, device=dev) if want_seg else None
     args = (_ptr(ids), _index_code(ids), n, _ptr(offsets), batch, num_tables, _ptr(row_base),
             total_rows, key_modulus)
-    wsb = ctypes.c_size_t(0)
-    _check("ctr_unique_ids", lib.ctr_unique_ids(*args, None, None, None, None, None, None,
-                                                ctypes.byref(wsb), None))
-    ws = workspace if workspace is not None and workspace.numel() >= wsb.value else _workspace(wsb.value, dev)
+    if workspace is None:
+        workspace = _workspace(unique_workspace_bytes(n), dev)
+    ws = workspace
     wsb = ctypes.c_size_t(ws.numel())
     _check("ctr_unique_ids", lib.ctr_unique_ids(*args, _ptr(uniq), _ptr(inv), _ptr(nu),
                                                 _ptr(perm), _ptr(seg), _ptr(ws),
@@ -177,9 +198,9 @@ def ctr_embbag_bwd(grad: torch.Tensor, grad_stride_b: int, grad_stride_t: int,
         row_grads = torch.empty((max(nnz, 1), dim), dtype=torch.float32, device=dev)
     args = (_ptr(grad), grad_stride_b, grad_stride_t, _ptr(offsets), batch, num_tables, dim, nnz,
             _ptr(perm), _ptr(inverse), _ptr(num_unique), _ptr(row_grads))
-    wsb = ctypes.c_size_t(0)
-    _check("ctr_embbag_bwd", lib.ctr_embbag_bwd(*args, None, ctypes.byref(wsb), None))
-    ws = workspace if workspace is not None and workspace.numel() >= wsb.value else _workspace(wsb.value, dev)
+    if workspace is None:
+        workspace = _workspace(embbag_bwd_workspace_bytes(nnz, dim), dev)
+    ws = workspace
     wsb = ctypes.c_size_t(ws.numel())
     _check("ctr_embbag_bwd", lib.ctr_embbag_bwd(*args, _ptr(ws), ctypes.byref(wsb), _stream(stream)))
     return row_grads

@@ -60,51 +60,114 @@ class FrontEnd:
             self.dout = _dev(w.grad_out.reshape(n, d), self.device)
         self.row_grads = torch.empty((max(self.nnz, 1), d), dtype=torch.float32,
                                      device=self.device)
-        self.ws_unique = None
-        self.ws_bwd = None
-        self.uniq = self.inverse = self.num_unique = self.perm = self.seg = None
+        n = self.nnz
+        dv = self.device
+        self.ws_unique = torch.empty(max(ctr.unique_workspace_bytes(n), 256), dtype=torch.uint8,
+                                     device=dv)
+        self.ws_bwd = torch.empty(max(ctr.embbag_bwd_workspace_bytes(n, d), 256),
+                                  dtype=torch.uint8, device=dv)
+        self.uniq = torch.empty(max(n, 1), dtype=torch.int64, device=dv)
+        self.inverse = torch.empty(max(n, 1), dtype=torch.int32, device=dv)
+        self.num_unique = torch.zeros(1, dtype=torch.int32, device=dv)
+        self.perm = torch.empty(max(n, 1), dtype=torch.int32, device=dv)
+        self.seg = torch.empty(n + 1, dtype=torch.int32, device=dv)
+        self._unique_out = (self.uniq, self.inverse, self.num_unique, self.perm, self.seg)
+        self.side = None
 
     # ------------------------------------------------------------------ steps of the path
     def unique(self):
         w = self.w
         if w.interaction:
-            res = ctr.ctr_unique_ids(self.indices, offsets=self.offsets, batch=w.batch,
-                                     num_tables=w.num_tables, row_base=self.row_base,
-                                     total_rows=w.total_rows, workspace=self.ws_unique)
+            ctr.ctr_unique_ids(self.indices, offsets=self.offsets, batch=w.batch,
+                               num_tables=w.num_tables, row_base=self.row_base,
+                               total_rows=w.total_rows, workspace=self.ws_unique,
+                               out=self._unique_out)
         else:
-            res = ctr.ctr_unique_ids(self.indices, key_modulus=w.key_modulus,
-                                     workspace=self.ws_unique)
-        self.uniq, self.inverse, self.num_unique, self.perm, self.seg = res
+            ctr.ctr_unique_ids(self.indices, key_modulus=w.key_modulus, workspace=self.ws_unique,
+                               out=self._unique_out)
 
-    def forward(self):
+    def _embbag_fwd(self):
         w = self.w
         if w.interaction:
             F, d = w.F, w.dim
             ctr.ctr_embbag_fwd(self.table, self.indices, self.offsets, w.batch, w.num_tables,
                                self.Z[:, 1:, :], F * d, d, row_base=self.row_base)
-            ctr.ctr_dot_interaction_fwd(self.Z, self.compute, self.R)
         else:
-            self.unique()
-            ctr.ctr_gather_rows(self.table, self.uniq, self.num_unique, self.nnz, out=self.E)
             ctr.ctr_embbag_fwd(self.E, self.inverse, self.offsets, self.nnz, 1, self.out,
                                w.dim, 0)
 
-    def backward(self):
+    def _gather_rows(self):
+        ctr.ctr_gather_rows(self.table, self.uniq, self.num_unique, self.nnz, out=self.E)
+
+    def _interaction_fwd(self):
+        ctr.ctr_dot_interaction_fwd(self.Z, self.compute, self.R)
+
+    def _interaction_bwd(self):
+        ctr.ctr_dot_interaction_bwd(self.Z, self.dR, self.compute, self.dZ)
+
+    def _embbag_bwd(self):
         w = self.w
         d = w.dim
+        perm = self.perm[:self.nnz]
         if w.interaction:
             F = w.F
-            ctr.ctr_dot_interaction_bwd(self.Z, self.dR, self.compute, self.dZ)
-            self.unique()
             ctr.ctr_embbag_bwd(self.dZ[:, 1:, :], F * d, d, self.offsets, w.batch,
-                               w.num_tables, d, self.perm, self.inverse, self.num_unique,
+                               w.num_tables, d, perm, self.inverse, self.num_unique,
                                self.row_grads, workspace=self.ws_bwd)
         else:
-            ctr.ctr_embbag_bwd(self.dout, d, 0, self.offsets, self.nnz, 1, d, self.perm,
+            ctr.ctr_embbag_bwd(self.dout, d, 0, self.offsets, self.nnz, 1, d, perm,
                                self.inverse, self.num_unique, self.row_grads,
                                workspace=self.ws_bwd)
-        ctr.ctr_sparse_sgd(self.table, self.uniq, self.num_unique, self.nnz, self.row_grads, w.lr)
 
-    def step(self):
-        self.forward()
-        self.backward()
+    def _sparse_sgd(self):
+        ctr.ctr_sparse_sgd(self.table, self.uniq, self.num_unique, self.nnz, self.row_grads,
+                           self.w.lr)
+
+    def stages(self):
+        """The step's calls in dependency order, as (name, fn)."""
+        if self.w.interaction:
+            return [("embbag_fwd", self._embbag_fwd), ("interaction_fwd", self._interaction_fwd),
+                    ("interaction_bwd", self._interaction_bwd), ("unique", self.unique),
+                    ("embbag_bwd", self._embbag_bwd), ("sparse_sgd", self._sparse_sgd)]
+        return [("unique", self.unique), ("gather_rows", self._gather_rows),
+                ("embbag_fwd", self._embbag_fwd), ("embbag_bwd", self._embbag_bwd),
+                ("sparse_sgd", self._sparse_sgd)]
+
+    def forward(self):
+        if self.w.interaction:
+            self._embbag_fwd()
+            self._interaction_fwd()
+        else:
+            self.unique()
+            self._gather_rows()
+            self._embbag_fwd()
+
+    def backward(self):
+        if self.w.interaction:
+            self._interaction_bwd()
+            self.unique()
+        self._embbag_bwd()
+        self._sparse_sgd()
+
+    def step(self, mark=None):
+        """One training step.  With tables and a dense vector, the batch's unique runs on a
+        second stream (default priority) beside the forward and the interaction gradient,
+        which do not need it.  ``mark(name, fn)`` may wrap a stage (e.g. with events on the
+        stream it runs on); by default it just calls it."""
+        run = mark if mark is not None else (lambda name, fn: fn())
+        if not self.w.interaction:
+            for name, fn in self.stages():
+                run(name, fn)
+            return
+        main = torch.cuda.current_stream(self.device)
+        if self.side is None:
+            self.side = torch.cuda.Stream(device=self.device)
+        self.side.wait_stream(main)
+        with torch.cuda.stream(self.side):
+            run("unique", self.unique)
+        run("embbag_fwd", self._embbag_fwd)
+        run("interaction_fwd", self._interaction_fwd)
+        run("interaction_bwd", self._interaction_bwd)
+        main.wait_stream(self.side)
+        run("embbag_bwd", self._embbag_bwd)
+        run("sparse_sgd", self._sparse_sgd)
