@@ -49,15 +49,17 @@ def stage_bytes(w, U):
             "interaction_fwd": 4 * B * F * d + 4 * B * (d + P),
             "interaction_bwd": 4 * B * (d + P) + 8 * B * F * d,
             "unique": 8 * n + 8 * (nb + 1) + 4 * n + 4 * n + 12 * U + 4 * U,
-            "embbag_bwd": 4 * n * d + 4 * n + 4 * n + 8 * (nb + 1) + 4 * U * d,
+            "embbag_bwd": 4 * n * d + 8 * n + 4 * U * d,
             "sparse_sgd": 2 * U * rb + 4 * U * d + 8 * U,
+            "embbag_bwd_sgd": 4 * n * d + 8 * n + 8 * U + 2 * U * rb,
         }
     return {
         "unique": 8 * n + 4 * n + 4 * n + 12 * U + 4 * U,
         "gather_rows": U * rb + 8 * U + 4 * U * d,
         "embbag_fwd": n * 4 * d + 4 * n + 8 * (n + 1) + 4 * n * d,
-        "embbag_bwd": 4 * n * d + 4 * n + 4 * n + 8 * (n + 1) + 4 * U * d,
+        "embbag_bwd": 4 * n * d + 8 * n + 4 * U * d,
         "sparse_sgd": 2 * U * rb + 4 * U * d + 8 * U,
+        "embbag_bwd_sgd": 4 * n * d + 8 * n + 8 * U + 2 * U * rb,
     }
 
 
@@ -70,13 +72,21 @@ def cpu_baseline(w, seconds: float):
     import numpy as np
     from oracle import oracle as orc
 
+    from sparse_embedding_lookup_amd import workloads
+
     threads = orc.get_threads()
     tab = orc.Table(w.rows, w.dim, w.dtype, w.table_seed)
     if w.total_rows * w.dim * 4 <= (4 << 30):
         tab = orc.Table(w.rows, w.dim, w.dtype, w.table_seed, data=orc.full_table(tab))
         sample_tab = "host copy of the tables"
+        budget = 8_000_000
     else:
         sample_tab = "rows regenerated from the counter-based fill"
+        budget = 400_000
+    if w.nnz > budget:                     # bound the CPU work: first b samples of the batch
+        b = max(1, int(w.batch * budget / w.nnz))
+        sample_tab += ", first %d of the %d samples" % (b, w.batch)
+        w = workloads.slice_batch(w, b)
 
     def one_step():
         if w.interaction:
@@ -110,7 +120,7 @@ def cpu_baseline(w, seconds: float):
         if el >= seconds or reps >= 1000:
             break
     return {"value": reps * w.nnz / el, "unit": "rows/s", "cores": threads, "kind": "oracle",
-            "sample": "%d full oracle step(s) of the same batch (%d rows each, %s) in %.1f s"
+            "sample": "%d oracle step(s) over the same batch (%d rows each, %s) in %.1f s"
                       % (reps, w.nnz, sample_tab, el),
             "seconds_per_step": el / reps}
 
@@ -124,6 +134,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--detail", default="", help="write per-stage detail JSON here")
+    ap.add_argument("--graph", action="store_true",
+                    help="replay captured HIP graph segments instead of launching from the host")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -146,42 +158,75 @@ def main():
         fe.step()
     torch.cuda.synchronize()
     U = int(fe.num_unique.cpu()[0])
-
-    # Per-stage durations from HIP events (diagnostic pass, not the timed region).
     K = args.steps
-    evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-            for _ in st] for _ in range(K)]
+
+    # Per-stage durations (diagnostic, before the timed region): each stage alone, as a
+    # captured graph in graph mode, bracketed by HIP events on the stream it runs on.
+    names = [n for n, _ in st]
+    if (not args.graph):
+        stage_runs = {n: (lambda n=n: fe.run([n])) for n in names}
+    else:
+        stage_graphs = {n: fe.capture([n]) for n in names}
+        stage_runs = {n: stage_graphs[n].replay for n in names}
+    evs = {n: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(K)] for n in names}
     for k in range(K):
-        for (name, fn), (e0, e1) in zip(st, evs[k]):
+        for n in names:
+            e0, e1 = evs[n][k]
             e0.record()
-            fn()
+            stage_runs[n]()
             e1.record()
     torch.cuda.synchronize()
-    stage_ms = {name: sum(evs[k][i][0].elapsed_time(evs[k][i][1]) for k in range(K)) / K
-                for i, (name, _) in enumerate(st)}
+    stage_ms = {n: sum(e0.elapsed_time(e1) for e0, e1 in evs[n]) / K for n in names}
     byts = stage_bytes(w, U)
     dominant = max((s for s in stage_ms if s in SINGLE_KERNEL), key=lambda s: stage_ms[s])
 
-    # Timed region: K whole steps as the pipeline runs them (unique on a second stream for
-    # the DLRM-shaped step); events bracket the dominant kernel on the stream it runs on.
-    print("[bench] timing %d steps" % K, file=sys.stderr, flush=True)
+    # Timed region: K whole steps.  Graph mode replays the step as three captured segments,
+    # [stages before the dominant kernel] [the dominant kernel] [the rest], with HIP events
+    # recorded between the launches, on the stream the dominant kernel runs on.
+    print("[bench] timing %d steps (%s)" % (K, "eager" if (not args.graph) else "graph"),
+          file=sys.stderr, flush=True)
     dev0 = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
     dev1 = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
-    cur = [0]
+    if (not args.graph):
+        cur = [0]
 
-    def mark(name, fn):
-        if name == dominant:
-            dev0[cur[0]].record()
-            fn()
-            dev1[cur[0]].record()
-        else:
-            fn()
+        def mark(name, fn):
+            if name == dominant:
+                dev0[cur[0]].record()
+                fn()
+                dev1[cur[0]].record()
+            else:
+                fn()
+
+        def one_step(k):
+            cur[0] = k
+            fe.step(mark)
+    else:
+        pre, post = fe.split(dominant)
+        g_pre = fe.capture(pre) if pre else None
+        g_dom = fe.capture([dominant])
+        g_post = fe.capture(post) if post else None
+        for _ in range(args.warmup):
+            if g_pre:
+                g_pre.replay()
+            g_dom.replay()
+            if g_post:
+                g_post.replay()
+
+        def one_step(k):
+            if g_pre:
+                g_pre.replay()
+            dev0[k].record()
+            g_dom.replay()
+            dev1[k].record()
+            if g_post:
+                g_post.replay()
 
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k in range(K):
-        cur[0] = k
-        fe.step(mark)
+        one_step(k)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_step = (t1 - t0) * 1e3 / K
@@ -202,6 +247,7 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "launch": "eager" if (not args.graph) else "hip-graph segments",
         "data": "synthetic (seeded; tables from the counter-based fill)",
         "config": {"workload": WORKLOAD_NAMES[args.config], "name": args.config,
                    "batch": w.batch, "tables": w.num_tables, "dim": w.dim, "nnz": w.nnz,

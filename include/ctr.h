@@ -89,6 +89,10 @@ const char* ctr_last_error(void);
  *                    (nullable)
  *   seg_offsets[u]   first sorted position of uniq[u]; seg_offsets[U] = n      int32 [n+1]
  *                    (nullable)
+ *   sorted_src[2p], sorted_src[2p+1]  (u, bag) of the occurrence at sorted position p,
+ *                    int32 pairs [n] (nullable; 8-byte aligned).  The bag is t*batch + b
+ *                    when offsets are given, else the occurrence index itself.  This is the
+ *                    input ctr_embbag_bwd needs, produced here at no extra pass.
  * Key range: with row_base the keys must lie in [0, total_rows); with only a modulus in
  * [0, key_modulus); otherwise any int64.  The sort covers only the live key bits.
  * n == 0 is legal: U = 0, seg_offsets[0] = 0.
@@ -97,7 +101,7 @@ int32_t ctr_unique_ids(const void* ids, int32_t id_type, int64_t n,
                        const int64_t* offsets, int64_t batch, int32_t num_tables,
                        const int64_t* row_base, int64_t total_rows, int64_t key_modulus,
                        int64_t* uniq, int32_t* inverse, int32_t* num_unique,
-                       int32_t* perm, int32_t* seg_offsets,
+                       int32_t* perm, int32_t* seg_offsets, int32_t* sorted_src,
                        void* workspace, size_t* workspace_bytes, void* stream);
 
 /*
@@ -130,16 +134,34 @@ int32_t ctr_embbag_fwd(const void* table, int32_t dtype, int64_t total_rows, int
  * "Synchronous Architecture": only rows present in the batch receive anything).
  *   row_grads[u, c] = sum over occurrences i with inverse[i] == u of
  *                     grad[b(i)*grad_stride_b + t(i)*grad_stride_t + c]
- * where bag (t(i), b(i)) holds occurrence i.  perm and inverse are ctr_unique_ids outputs
- * for the same occurrences; the sum runs in sorted order as a fixed-shape tree over
- * chunks (deterministic, no atomics).  row_grads: fp32 [nnz, dim]; rows u >= U untouched.
- * Workspace: two-call query.
+ * where bag (t(i), b(i)) holds occurrence i.  The grouping comes from ctr_unique_ids for the
+ * same occurrences: either its sorted_src pairs (preferred: read in order), or perm and
+ * inverse (then the bags are expanded from offsets and gathered in sorted order here).
+ * The sum runs in sorted order as a fixed-shape tree over chunks (deterministic, no
+ * atomics).  row_grads: fp32 [nnz, dim]; rows u >= U untouched.  Workspace: two-call query.
  */
 int32_t ctr_embbag_bwd(const float* grad, int64_t grad_stride_b, int64_t grad_stride_t,
                        const int64_t* offsets, int64_t batch, int32_t num_tables, int32_t dim,
                        int64_t nnz, const int32_t* perm, const int32_t* inverse,
-                       const int32_t* num_unique, float* row_grads,
+                       const int32_t* sorted_src, const int32_t* num_unique, float* row_grads,
                        void* workspace, size_t* workspace_bytes, void* stream);
+
+/*
+ * ctr_embbag_bwd_sgd -- ctr_embbag_bwd and ctr_sparse_sgd in one pass: the moment the
+ * reduce-by-key completes the gradient of distinct row u it applies
+ *   table[uniq[u], :] = round(table[uniq[u], :] - lr * g[u, :])
+ * with exactly the arithmetic of ctr_sparse_sgd (so the table ends bit-identical to the
+ * two-call path), without writing g to memory and reading it back.  row_grads is optional
+ * (NULL: gradients are not kept).  Grouping from ctr_unique_ids' sorted_src and uniq.
+ * dtype/total_rows/dim describe the table as in ctr_sparse_sgd; dim <= 1024.  Workspace:
+ * two-call query, same size as ctr_embbag_bwd.
+ */
+int32_t ctr_embbag_bwd_sgd(const float* grad, int64_t grad_stride_b, int64_t grad_stride_t,
+                           const int64_t* offsets, int64_t batch, int32_t num_tables,
+                           int64_t nnz, const int32_t* sorted_src, const int32_t* num_unique,
+                           void* table, int32_t dtype, int64_t total_rows, int32_t dim,
+                           const int64_t* uniq, float lr, float* row_grads, void* workspace,
+                           size_t* workspace_bytes, void* stream);
 
 /*
  * ctr_sparse_sgd -- update of the touched rows only ([TN] "Synchronous Architecture"):

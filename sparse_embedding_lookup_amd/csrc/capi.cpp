@@ -75,8 +75,8 @@ int32_t ctr_unique_ids(const void* ids, int32_t id_type, int64_t n, const int64_
                        int64_t batch, int32_t num_tables, const int64_t* row_base,
                        int64_t total_rows, int64_t key_modulus, int64_t* uniq,
                        int32_t* inverse, int32_t* num_unique, int32_t* perm,
-                       int32_t* seg_offsets, void* workspace, size_t* workspace_bytes,
-                       void* stream) {
+                       int32_t* seg_offsets, int32_t* sorted_src, void* workspace,
+                       size_t* workspace_bytes, void* stream) {
   g_msg[0] = 0;
   if (!workspace_bytes) return fail(CTR_ERR_INVALID_ARGUMENT, "workspace_bytes is NULL");
   if (n < 0 || n > kMaxElems) return fail(CTR_ERR_INVALID_ARGUMENT, "n=%lld out of [0, 2^31)", (long long)n);
@@ -91,7 +91,7 @@ int32_t ctr_unique_ids(const void* ids, int32_t id_type, int64_t n, const int64_
       return fail(CTR_ERR_INVALID_ARGUMENT, "bad batch %lld", (long long)batch);
     if (total_rows < 1) return fail(CTR_ERR_INVALID_ARGUMENT, "total_rows must be >= 1");
   }
-  const size_t need = ctr::unique_workspace_bytes(n, perm != nullptr);
+  const size_t need = ctr::unique_workspace_bytes(n);
   if (!workspace) {
     *workspace_bytes = need;
     return CTR_OK;
@@ -101,6 +101,8 @@ int32_t ctr_unique_ids(const void* ids, int32_t id_type, int64_t n, const int64_
   if (!num_unique) return fail(CTR_ERR_INVALID_ARGUMENT, "num_unique is NULL");
   if (n > 0 && (!ids || !uniq || !inverse))
     return fail(CTR_ERR_INVALID_ARGUMENT, "ids, uniq and inverse are required");
+  if (sorted_src && (reinterpret_cast<uintptr_t>(sorted_src) & 7u))
+    return fail(CTR_ERR_UNSUPPORTED, "sorted_src is not 8-byte aligned");
   int bits;
   bool is_signed = false;
   if (row_base) {
@@ -114,7 +116,8 @@ int32_t ctr_unique_ids(const void* ids, int32_t id_type, int64_t n, const int64_
   if (bits < 1) bits = 1;
   return hip_status(ctr::launch_unique(ids, id_type == CTR_I64, n, offsets, batch, num_tables,
                                        row_base, key_modulus, bits, is_signed, uniq, inverse,
-                                       num_unique, perm, seg_offsets, workspace,
+                                       num_unique, perm, seg_offsets,
+                                       reinterpret_cast<int2*>(sorted_src), workspace,
                                        (hipStream_t)stream),
                     "ctr_unique_ids");
 }
@@ -165,8 +168,8 @@ int32_t ctr_embbag_fwd(const void* table, int32_t dtype, int64_t total_rows, int
 int32_t ctr_embbag_bwd(const float* grad, int64_t grad_stride_b, int64_t grad_stride_t,
                        const int64_t* offsets, int64_t batch, int32_t num_tables, int32_t dim,
                        int64_t nnz, const int32_t* perm, const int32_t* inverse,
-                       const int32_t* num_unique, float* row_grads, void* workspace,
-                       size_t* workspace_bytes, void* stream) {
+                       const int32_t* sorted_src, const int32_t* num_unique, float* row_grads,
+                       void* workspace, size_t* workspace_bytes, void* stream) {
   g_msg[0] = 0;
   if (!workspace_bytes) return fail(CTR_ERR_INVALID_ARGUMENT, "workspace_bytes is NULL");
   if (dim <= 0) return fail(CTR_ERR_INVALID_ARGUMENT, "dim must be positive");
@@ -186,8 +189,12 @@ int32_t ctr_embbag_bwd(const float* grad, int64_t grad_stride_b, int64_t grad_st
   if (*workspace_bytes < need)
     return fail(CTR_ERR_WORKSPACE_TOO_SMALL, "workspace %zu < %zu bytes", *workspace_bytes, need);
   if (!offsets || !num_unique) return fail(CTR_ERR_INVALID_ARGUMENT, "offsets and num_unique are required");
-  if (nnz > 0 && (!grad || !perm || !inverse || !row_grads))
-    return fail(CTR_ERR_INVALID_ARGUMENT, "grad, perm, inverse and row_grads are required");
+  if (nnz > 0 && (!grad || !row_grads))
+    return fail(CTR_ERR_INVALID_ARGUMENT, "grad and row_grads are required");
+  if (nnz > 0 && !sorted_src && (!perm || !inverse))
+    return fail(CTR_ERR_INVALID_ARGUMENT, "either sorted_src or perm and inverse are required");
+  if (sorted_src && (reinterpret_cast<uintptr_t>(sorted_src) & 7u))
+    return fail(CTR_ERR_UNSUPPORTED, "sorted_src is not 8-byte aligned");
   if (grad_stride_b < 0 || grad_stride_t < 0)
     return fail(CTR_ERR_INVALID_ARGUMENT, "negative gradient stride");
   if ((grad && !aligned16(grad)) || (row_grads && !aligned16(row_grads)) || grad_stride_b % 4 ||
@@ -195,9 +202,55 @@ int32_t ctr_embbag_bwd(const float* grad, int64_t grad_stride_b, int64_t grad_st
     return fail(CTR_ERR_UNSUPPORTED, "grad/row_grads must be 16-byte aligned, strides multiple of 4");
   if (!aligned16(workspace)) return fail(CTR_ERR_UNSUPPORTED, "workspace is not 16-byte aligned");
   return hip_status(ctr::launch_embbag_bwd(grad, grad_stride_b, grad_stride_t, offsets, batch,
-                                           num_tables, dim, nnz, perm, inverse, num_unique,
-                                           row_grads, workspace, (hipStream_t)stream),
+                                           num_tables, dim, nnz, perm, inverse,
+                                           reinterpret_cast<const int2*>(sorted_src), num_unique,
+                                           row_grads, nullptr, 0, 0, nullptr, 0.f, workspace,
+                                           (hipStream_t)stream),
                     "ctr_embbag_bwd");
+}
+
+int32_t ctr_embbag_bwd_sgd(const float* grad, int64_t grad_stride_b, int64_t grad_stride_t,
+                           const int64_t* offsets, int64_t batch, int32_t num_tables,
+                           int64_t nnz, const int32_t* sorted_src, const int32_t* num_unique,
+                           void* table, int32_t dtype, int64_t total_rows, int32_t dim,
+                           const int64_t* uniq, float lr, float* row_grads, void* workspace,
+                           size_t* workspace_bytes, void* stream) {
+  g_msg[0] = 0;
+  if (!workspace_bytes) return fail(CTR_ERR_INVALID_ARGUMENT, "workspace_bytes is NULL");
+  int32_t st = check_table(table, dtype, total_rows, dim);
+  if (st) return st;
+  if (dim > 1024) return fail(CTR_ERR_UNSUPPORTED, "dim %d above 1024", dim);
+  if (nnz < 0 || nnz > kMaxElems) return fail(CTR_ERR_INVALID_ARGUMENT, "bad nnz");
+  if (num_tables < 1) return fail(CTR_ERR_INVALID_ARGUMENT, "num_tables must be >= 1");
+  if (batch < 0 || (int64_t)num_tables * batch > kMaxElems)
+    return fail(CTR_ERR_INVALID_ARGUMENT, "bad batch");
+  if (nnz > 0 && batch == 0)
+    return fail(CTR_ERR_INVALID_ARGUMENT, "nnz > 0 needs at least one bag");
+  const size_t need = ctr::embbag_bwd_workspace_bytes(nnz, dim);
+  if (!workspace) {
+    *workspace_bytes = need;
+    return CTR_OK;
+  }
+  if (*workspace_bytes < need)
+    return fail(CTR_ERR_WORKSPACE_TOO_SMALL, "workspace %zu < %zu bytes", *workspace_bytes, need);
+  if (!offsets || !num_unique) return fail(CTR_ERR_INVALID_ARGUMENT, "offsets and num_unique are required");
+  if (nnz > 0 && (!grad || !sorted_src || !uniq))
+    return fail(CTR_ERR_INVALID_ARGUMENT, "grad, sorted_src and uniq are required");
+  if (!std::isfinite(lr)) return fail(CTR_ERR_INVALID_ARGUMENT, "lr is not finite");
+  if (grad_stride_b < 0 || grad_stride_t < 0)
+    return fail(CTR_ERR_INVALID_ARGUMENT, "negative gradient stride");
+  if ((grad && !aligned16(grad)) || (row_grads && !aligned16(row_grads)) || grad_stride_b % 4 ||
+      grad_stride_t % 4)
+    return fail(CTR_ERR_UNSUPPORTED, "grad/row_grads must be 16-byte aligned, strides multiple of 4");
+  if (reinterpret_cast<uintptr_t>(sorted_src) & 7u)
+    return fail(CTR_ERR_UNSUPPORTED, "sorted_src is not 8-byte aligned");
+  if (!aligned16(workspace)) return fail(CTR_ERR_UNSUPPORTED, "workspace is not 16-byte aligned");
+  return hip_status(ctr::launch_embbag_bwd(grad, grad_stride_b, grad_stride_t, offsets, batch,
+                                           num_tables, dim, nnz, nullptr, nullptr,
+                                           reinterpret_cast<const int2*>(sorted_src), num_unique,
+                                           row_grads, table, dtype == CTR_BF16 ? 2 : 1,
+                                           total_rows, uniq, lr, workspace, (hipStream_t)stream),
+                    "ctr_embbag_bwd_sgd");
 }
 
 int32_t ctr_sparse_sgd(void* table, int32_t dtype, int64_t total_rows, int32_t dim,

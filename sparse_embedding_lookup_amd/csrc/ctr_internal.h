@@ -15,12 +15,10 @@ constexpr int kWave = 64;
 __device__ __forceinline__ float bf16_lo(uint32_t pair) { return __uint_as_float(pair << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t pair) { return __uint_as_float(pair & 0xFFFF0000u); }
 
-// binary32 -> bf16, round to nearest, ties to even (NaN stays a quiet NaN).
+// binary32 -> bf16, round to nearest, ties to even (NaN stays a quiet NaN).  On gfx950 the
+// conversion is the hardware v_cvt_pk_bf16_f32 under the default round-to-nearest-even mode.
 __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (u >> 16) | 0x40u;
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return u >> 16;
+  return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)f);
 }
 
 __device__ __forceinline__ float qnan() { return __uint_as_float(0x7FC00000u); }
@@ -81,12 +79,13 @@ inline RowGeom row_geom(int64_t vecs) {
 // Each returns hipSuccess or the launch error.  Shapes are validated by the caller.
 
 // unique.hip
-size_t unique_workspace_bytes(int64_t n, bool need_perm);
+size_t unique_workspace_bytes(int64_t n);
 hipError_t launch_unique(const void* ids, bool ids64, int64_t n, const int64_t* offsets,
                          int64_t batch, int32_t num_tables, const int64_t* row_base,
                          int64_t modulus, int key_bits, bool key_signed, int64_t* uniq,
                          int32_t* inverse, int32_t* num_unique, int32_t* perm,
-                         int32_t* seg_offsets, void* workspace, hipStream_t s);
+                         int32_t* seg_offsets, int2* sorted_src, void* workspace,
+                         hipStream_t s);
 
 // embbag.hip
 hipError_t launch_embbag_fwd(const void* table, bool bf16, int64_t total_rows, int dim,
@@ -109,9 +108,10 @@ hipError_t launch_validate_csr(const void* idx, bool idx64, int64_t nnz, const i
 size_t embbag_bwd_workspace_bytes(int64_t nnz, int dim);
 hipError_t launch_embbag_bwd(const float* grad, int64_t sb, int64_t st, const int64_t* offsets,
                              int64_t batch, int32_t num_tables, int dim, int64_t nnz,
-                             const int32_t* perm, const int32_t* inverse,
-                             const int32_t* num_unique, float* row_grads, void* workspace,
-                             hipStream_t s);
+                             const int32_t* perm, const int32_t* inverse, const int2* sorted_src,
+                             const int32_t* num_unique, float* row_grads, void* table,
+                             int sgd_mode, int64_t total_rows, const int64_t* uniq, float lr,
+                             void* workspace, hipStream_t s);
 
 // interaction.hip
 bool interaction_bf16_supported(int F, int dim);

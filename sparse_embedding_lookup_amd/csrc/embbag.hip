@@ -19,65 +19,113 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kUnroll = 8;
 
+// Raw 16 bytes of a row (4 fp32 or 8 bf16), widened only when accumulated.
+template <bool BF16>
+__device__ __forceinline__ void accumulate(float* acc, const uint4& x) {
+  if (BF16) {
+    acc[0] += bf16_lo(x.x); acc[1] += bf16_hi(x.x);
+    acc[2] += bf16_lo(x.y); acc[3] += bf16_hi(x.y);
+    acc[4] += bf16_lo(x.z); acc[5] += bf16_hi(x.z);
+    acc[6] += bf16_lo(x.w); acc[7] += bf16_hi(x.w);
+  } else {
+    acc[0] += __uint_as_float(x.x); acc[1] += __uint_as_float(x.y);
+    acc[2] += __uint_as_float(x.z); acc[3] += __uint_as_float(x.w);
+  }
+}
+
+constexpr int kMaxBagsPerGroup = 16;
+
+// A group of G lanes pools `nbg` consecutive bags: their offsets and table bases go to LDS,
+// their occurrences are walked in order in chunks of kU (indices loaded cooperatively and
+// broadcast by shuffles, kU row loads in flight), and a bag's sum is stored when the walk
+// passes its end.  Rows of a bag are added in occurrence order.
 template <typename TIdx, bool BF16, int G, int VPL>
 __global__ __launch_bounds__(kThreads) void embbag_fwd_kernel(
     const char* __restrict__ table, int64_t total_rows, int64_t row_bytes, int vecs,
     const int64_t* __restrict__ row_base, const TIdx* __restrict__ idx, int64_t nnz,
-    const int64_t* __restrict__ offsets, int64_t batch, int64_t num_bags,
+    const int64_t* __restrict__ offsets, int64_t batch, int64_t num_bags, int nbg,
     float* __restrict__ out, int64_t sb, int64_t st) {
-  using V = Vec<BF16>;
-  constexpr int E = V::kElems;
+  constexpr int E = BF16 ? 8 : 4;
+  constexpr int kGroups = kThreads / G;
+  constexpr int kU = (VPL == 1 && G <= 8) ? 16 : 8;   // rows in flight per group
+  constexpr int kRegs = (kU + G - 1) / G;
+  __shared__ int32_t s_off[kGroups][kMaxBagsPerGroup + 1];     // nnz < 2^31
+  __shared__ int64_t s_base[kGroups][kMaxBagsPerGroup];
   const int lane = threadIdx.x & (G - 1);
-  const int64_t bag = (int64_t)blockIdx.x * (kThreads / G) + threadIdx.x / G;
-  if (bag >= num_bags) return;
-  const int64_t t = bag / batch;
-  const int64_t b = bag - t * batch;
-  const int64_t beg = clamp64(offsets[bag], 0, nnz);
-  const int64_t end = clamp64(offsets[bag + 1], beg, nnz);
-  const int64_t base = row_base ? row_base[t] : 0;
+  const int grp = threadIdx.x / G;
+  const int lane0 = (threadIdx.x & 63) & ~(G - 1);
+  const int64_t s0 = ((int64_t)blockIdx.x * kGroups + grp) * nbg;
+  const int nb = (int)clamp64(num_bags - s0, 0, nbg);
+  for (int j = lane; j <= nb; j += G) s_off[grp][j] = (int32_t)clamp64(offsets[s0 + j], 0, nnz);
+  for (int j = lane; j < nb; j += G) s_base[grp][j] = row_base ? row_base[(s0 + j) / batch] : 0;
+  __syncthreads();
+  if (nb == 0) return;
 
+  const int64_t o_beg = s_off[grp][0];
+  const int64_t o_end = s_off[grp][nb] > o_beg ? s_off[grp][nb] : o_beg;
   float acc[VPL][E];
 #pragma unroll
-  for (int v = 0; v < VPL; ++v)
+  for (int a = 0; a < VPL; ++a)
 #pragma unroll
-    for (int e = 0; e < E; ++e) acc[v][e] = 0.f;
+    for (int e = 0; e < E; ++e) acc[a][e] = 0.f;
+  int cur = 0;
+  auto flush = [&](int j) {
+    const int64_t s = s0 + j;
+    const int64_t t = s / batch, b = s - t * batch;
+    float* o = out + b * sb + t * st;
+#pragma unroll
+    for (int a = 0; a < VPL; ++a) {
+      const int vi = a * G + lane;
+      if (vi < vecs) {
+        float4* p = reinterpret_cast<float4*>(o + (int64_t)vi * E);
+        p[0] = make_float4(acc[a][0], acc[a][1], acc[a][2], acc[a][3]);
+        if (E == 8) p[1] = make_float4(acc[a][4 % E], acc[a][5 % E], acc[a][6 % E], acc[a][7 % E]);
+      }
+#pragma unroll
+      for (int e = 0; e < E; ++e) acc[a][e] = 0.f;
+    }
+  };
 
-  for (int64_t k0 = beg; k0 < end; k0 += kUnroll) {
-    V r[kUnroll][VPL];
+  for (int64_t k0 = o_beg; k0 < o_end; k0 += kU) {
+    TIdx iv[kRegs];
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
+    for (int r = 0; r < kRegs; ++r) {
+      const int e = r * G + lane;
+      const int64_t k = k0 + e;
+      iv[r] = (e < kU && k < o_end) ? idx[k] : (TIdx)0;
+    }
+    uint4 rv[kU][VPL];
+    int bagu[kU];
+    int c = cur;
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
       const int64_t k = k0 + u;
-      const bool live = k < end;
-      const int64_t key = live ? base + (int64_t)idx[k] : 0;
+      while (c < nb - 1 && k >= s_off[grp][c + 1]) ++c;
+      bagu[u] = c;
+      const int64_t id = (int64_t)__shfl(iv[u / G], lane0 + (u % G), 64);
+      const int64_t key = s_base[grp][c] + id;
+      const bool live = k < o_end;
       const bool ok = key >= 0 && key < total_rows;
 #pragma unroll
-      for (int v = 0; v < VPL; ++v) {
-        const int vi = v * G + lane;
-        if (!live || vi >= vecs)
-          r[u][v].zero();
-        else if (!ok)
-          r[u][v].nan();
+      for (int a = 0; a < VPL; ++a) {
+        const int vi = a * G + lane;
+        if (live && ok && vi < vecs)
+          rv[u][a] = *reinterpret_cast<const uint4*>(table + key * row_bytes + (int64_t)vi * 16);
+        else if (live && !ok)
+          rv[u][a] = make_uint4(0x7FC00000u, 0x7FC00000u, 0x7FC00000u, 0x7FC00000u);  // NaN
         else
-          r[u][v].load(table + key * row_bytes + (int64_t)vi * 16);
+          rv[u][a] = make_uint4(0u, 0u, 0u, 0u);
       }
     }
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u)
+    for (int u = 0; u < kU; ++u) {
+      if (k0 + u >= o_end) break;
+      while (cur < bagu[u]) flush(cur++);
 #pragma unroll
-      for (int v = 0; v < VPL; ++v)
-#pragma unroll
-        for (int e = 0; e < E; ++e) acc[v][e] += r[u][v].v[e];
+      for (int a = 0; a < VPL; ++a) accumulate<BF16>(acc[a], rv[u][a]);
+    }
   }
-
-  float* o = out + b * sb + t * st;
-#pragma unroll
-  for (int v = 0; v < VPL; ++v) {
-    const int vi = v * G + lane;
-    if (vi >= vecs) continue;
-    float4* p = reinterpret_cast<float4*>(o + (int64_t)vi * E);
-    p[0] = make_float4(acc[v][0], acc[v][1], acc[v][2], acc[v][3]);
-    if (E == 8) p[1] = make_float4(acc[v][4 % E], acc[v][5 % E], acc[v][6 % E], acc[v][7 % E]);
-  }
+  while (cur < nb) flush(cur++);
 }
 
 // E[u] = W[rows[u]] widened to fp32, u < min(num_rows, capacity).
@@ -252,26 +300,35 @@ hipError_t launch_embbag_fwd(const void* table, bool bf16, int64_t total_rows, i
   const int64_t num_bags = (int64_t)num_tables * batch;
   if (num_bags == 0) return hipSuccess;
   const char* tb = static_cast<const char*>(table);
+  // Bags per lane group: about 64 occurrences per group, but keep >= 1024 blocks in flight.
+  const double avg = (double)nnz / (double)num_bags;
+  int nbg = (int)(64.0 / (avg > 1.0 ? avg : 1.0) + 0.5);
+  if (nbg > kMaxBagsPerGroup) nbg = kMaxBagsPerGroup;
   CTR_DISPATCH_G_VPL(rg.G, rg.VPL, {
-    const int64_t blocks = (num_bags + (kThreads / G) - 1) / (kThreads / G);
+    const int64_t groups_for_fill = (int64_t)(kThreads / G) * 1024;
+    const int64_t cap = num_bags / groups_for_fill;
+    if (nbg > cap) nbg = (int)cap;
+    if (nbg < 1) nbg = 1;
+    const int64_t per_block = (int64_t)(kThreads / G) * nbg;
+    const int64_t blocks = (num_bags + per_block - 1) / per_block;
     if (bf16) {
       if (idx64)
         embbag_fwd_kernel<int64_t, true, G, VPL><<<(unsigned)blocks, kThreads, 0, s>>>(
             tb, total_rows, row_bytes, vecs, row_base, (const int64_t*)idx, nnz, offsets,
-            batch, num_bags, out, sb, st);
+            batch, num_bags, nbg, out, sb, st);
       else
         embbag_fwd_kernel<int32_t, true, G, VPL><<<(unsigned)blocks, kThreads, 0, s>>>(
             tb, total_rows, row_bytes, vecs, row_base, (const int32_t*)idx, nnz, offsets,
-            batch, num_bags, out, sb, st);
+            batch, num_bags, nbg, out, sb, st);
     } else {
       if (idx64)
         embbag_fwd_kernel<int64_t, false, G, VPL><<<(unsigned)blocks, kThreads, 0, s>>>(
             tb, total_rows, row_bytes, vecs, row_base, (const int64_t*)idx, nnz, offsets,
-            batch, num_bags, out, sb, st);
+            batch, num_bags, nbg, out, sb, st);
       else
         embbag_fwd_kernel<int32_t, false, G, VPL><<<(unsigned)blocks, kThreads, 0, s>>>(
             tb, total_rows, row_bytes, vecs, row_base, (const int32_t*)idx, nnz, offsets,
-            batch, num_bags, out, sb, st);
+            batch, num_bags, nbg, out, sb, st);
     }
   });
   return hipGetLastError();

@@ -39,13 +39,19 @@ __device__ __forceinline__ int tri_index(int i, int j) {
   return i > j ? i * (i - 1) / 2 + j : j * (j - 1) / 2 + i;
 }
 
+// An empty asm that claims to change an offset: loads addressed through it stay where they
+// are written instead of being hoisted out of a loop, which bounds register pressure.
+__device__ __forceinline__ int pinned_zero() {
+  int z = 0;
+  asm volatile("" : "+v"(z));
+  return z;
+}
+
+// Eight fp32 values rounded to bf16 (nearest-even, hardware convert) as an MFMA operand.
 __device__ __forceinline__ bf16x8 pack_bf16x8(const float* x) {
-  u32x4 w;
-  w[0] = f32_to_bf16_bits(x[0]) | (f32_to_bf16_bits(x[1]) << 16);
-  w[1] = f32_to_bf16_bits(x[2]) | (f32_to_bf16_bits(x[3]) << 16);
-  w[2] = f32_to_bf16_bits(x[4]) | (f32_to_bf16_bits(x[5]) << 16);
-  w[3] = f32_to_bf16_bits(x[6]) | (f32_to_bf16_bits(x[7]) << 16);
-  return __builtin_bit_cast(bf16x8, w);
+  bf16x8 v = {(__bf16)x[0], (__bf16)x[1], (__bf16)x[2], (__bf16)x[3],
+              (__bf16)x[4], (__bf16)x[5], (__bf16)x[6], (__bf16)x[7]};
+  return v;
 }
 
 // ------------------------------------------------------------------------- fp32 forward
@@ -121,7 +127,31 @@ __global__ __launch_bounds__(kThreads) void interaction_bwd_f32_kernel(
 }
 
 // ------------------------------------------------------------------------- bf16 forward
-// FB: 32-row blocks covering F (F <= 32*FB); KS: dim / 16 (k-steps of 16).
+// Operand fragment of row-block I, k-step s: lane holds row 32*I + rl, columns
+// 16*s + 8*kg .. +8 of Z[b], rounded to bf16 (rows >= F are zero).
+template <int KS>
+__device__ __forceinline__ void load_row_block(const float* __restrict__ zb, int F, int I,
+                                               int rl, int kg, bf16x8* fr) {
+  constexpr int dim = KS * 16;
+  const int row = 32 * I + rl;
+#pragma unroll
+  for (int s = 0; s < KS; ++s) {
+    float x[8];
+    if (row < F) {
+      const float4* p = reinterpret_cast<const float4*>(zb + row * dim + 16 * s + 8 * kg);
+      const float4 a = p[0], c = p[1];
+      x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+      x[4] = c.x; x[5] = c.y; x[6] = c.z; x[7] = c.w;
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] = 0.f;
+    }
+    fr[s] = pack_bf16x8(x);
+  }
+}
+
+// FB: 32-row blocks covering F (F <= 32*FB); KS: dim / 16 (k-steps of 16).  Only two row
+// blocks of fragments are live at a time (the J block is re-read, from L1/L2).
 template <int FB, int KS>
 __global__ __launch_bounds__(kThreads) void interaction_fwd_mfma_kernel(
     const float* __restrict__ Z, int64_t batch, int F, float* __restrict__ R, int64_t r_stride) {
@@ -132,39 +162,29 @@ __global__ __launch_bounds__(kThreads) void interaction_fwd_mfma_kernel(
   const float* zb = Z + b * (int64_t)F * dim;
   float* rb = R + b * r_stride;
   const int rl = lane & 31, kg = lane >> 5;
-
-  // Operand fragments: lane holds row 32*I + rl, columns 16*s + 8*kg .. +8, as bf16.
-  bf16x8 fr[FB][KS];
-#pragma unroll
-  for (int I = 0; I < FB; ++I) {
-    const int row = 32 * I + rl;
-#pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      float x[8];
-      if (row < F) {
-        const float4* p = reinterpret_cast<const float4*>(zb + row * dim + 16 * s + 8 * kg);
-        const float4 a = p[0], c = p[1];
-        x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
-        x[4] = c.x; x[5] = c.y; x[6] = c.z; x[7] = c.w;
-      } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) x[e] = 0.f;
-      }
-      fr[I][s] = pack_bf16x8(x);
-    }
-  }
   for (int c = lane; c < dim; c += 64) rb[c] = zb[c];   // dense passthrough (exact)
 
 #pragma unroll
   for (int I = 0; I < FB; ++I) {
+    if (32 * I >= F) break;
+    bf16x8 fa[KS];
+    load_row_block<KS>(zb, F, I, rl, kg, fa);
 #pragma unroll
     for (int J = 0; J <= I; ++J) {
+      if (J == I && F - 32 * I < 2) break;          // no pair i > j inside this tile
+      bf16x8 fb[KS];
+      if (J == I) {
+#pragma unroll
+        for (int s = 0; s < KS; ++s) fb[s] = fa[s];
+      } else {
+        load_row_block<KS>(zb + pinned_zero(), F, J, rl, kg, fb);
+      }
       f32x16 acc;
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[v] = 0.f;
 #pragma unroll
       for (int s = 0; s < KS; ++s)
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[I][s], fr[J][s], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[s], fb[s], acc, 0, 0, 0);
       // acc[v] = D[m][n], m = 8*(v/4) + 4*kg + v%4 (row, from A = block I), n = rl (from B)
       const int j = 32 * J + rl;
 #pragma unroll
@@ -178,72 +198,90 @@ __global__ __launch_bounds__(kThreads) void interaction_fwd_mfma_kernel(
 
 // ------------------------------------------------------------------------- bf16 backward
 // One wave per sample; WPB samples per block; LDS holds each sample's pair gradients.
-template <int FB>
+// For each 32-row block of S (A operand, built once from LDS) and each 32-column slab of Z
+// (B operand, re-read per row block from L1/L2), 2*FB MFMAs give a 32x32 block of dZ.
+template <int FB, int KS>
 __global__ __launch_bounds__(kThreads) void interaction_bwd_mfma_kernel(
     const float* __restrict__ Z, const float* __restrict__ dR, int64_t dr_stride,
-    int64_t batch, int F, int dim, int wpb, float* __restrict__ dZ) {
+    int64_t batch, int F, int wpb, float* __restrict__ dZ) {
   constexpr int FKS = 2 * FB;             // k-steps of 16 over the padded F
+  constexpr int dim = KS * 16;
   extern __shared__ float sp_all[];
   const int lane = threadIdx.x & 63;
   const int wv = threadIdx.x >> 6;
   const int P = F * (F - 1) / 2;
   const int64_t b = (int64_t)blockIdx.x * wpb + wv;
   const bool live = wv < wpb && b < batch;
-  float* sp = sp_all + wv * P;
-  if (live)
+  float* sp = sp_all + wv * (P + 1);       // slot P holds 0: the diagonal and the padding
+  if (live) {
     for (int q = lane; q < P; q += 64) sp[q] = dR[b * dr_stride + dim + q];
+    if (lane == 0) sp[P] = 0.f;
+  }
   __syncthreads();
   if (!live) return;
   const float* zb = Z + b * (int64_t)F * dim;
   const int rl = lane & 31, kg = lane >> 5;
+  const int kmax = (F + 15) / 16;          // k-steps holding any row j < F
 
-  // A fragments: S[i = 32I + rl][j = 16s + 8kg + e]
-  bf16x8 af[FB][FKS];
-#pragma unroll
+  constexpr int nblk = (dim + 31) / 32;
+#pragma unroll 1
   for (int I = 0; I < FB; ++I) {
+    if (32 * I >= F) break;
     const int i = 32 * I + rl;
+    // A fragments of S for this row block, built once from the pair gradients in LDS
+    // Index arithmetic without compare masks: an invalid (i, j) (diagonal, or outside F)
+    // reads the zero slot P.
+    // (kgx is kg through an opaque zero, so j-dependent terms are not hoisted out of the
+    // loops and kept live across them)
+    const int vi = (int)((unsigned)(i - F) >> 31);             // 1 if i < F
+    const int kgx = kg + pinned_zero();
+    bf16x8 af[FKS];
 #pragma unroll
     for (int s = 0; s < FKS; ++s) {
       float x[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const int j = 16 * s + 8 * kg + e;
-        x[e] = (i < F && j < F && i != j) ? sp[tri_index(i, j)] : 0.f;
+        const int j = 16 * s + 8 * kgx + e;
+        const int vj = (int)((unsigned)(j - F) >> 31);           // 1 if j < F
+        const int ne = (int)((0u - (unsigned)(i ^ j)) >> 31);    // 1 if i != j
+        const int ok = vi & vj & ne;
+        const int q = ok * tri_index(i, j) + (1 - ok) * P;
+        x[e] = sp[q];
       }
-      af[I][s] = pack_bf16x8(x);
+      af[s] = pack_bf16x8(x);
     }
-  }
-  const int nblk = (dim + 31) / 32;
-  for (int nb = 0; nb < nblk; ++nb) {
-    const int n = 32 * nb + rl;
-    const bool nvalid = n < dim;
-    bf16x8 bfr[FKS];
-#pragma unroll
-    for (int s = 0; s < FKS; ++s) {
-      float x[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int j = 16 * s + 8 * kg + e;
-        x[e] = (j < F && nvalid) ? zb[j * dim + n] : 0.f;
-      }
-      bfr[s] = pack_bf16x8(x);
-    }
-#pragma unroll
-    for (int I = 0; I < FB; ++I) {
+#pragma unroll 1
+    for (int nb = 0; nb < nblk; ++nb) {
+      const int n = 32 * nb + rl;
+      const bool nvalid = n < dim;
+      const int kgy = kg + pinned_zero();
+      const float* zp = zb + pinned_zero();
       f32x16 acc;
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[v] = 0.f;
 #pragma unroll
-      for (int s = 0; s < FKS; ++s)
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[I][s], bfr[s], acc, 0, 0, 0);
+      for (int s = 0; s < FKS; ++s) {
+        if (s >= kmax) break;
+        float x[8];
+        const int cn = nvalid ? n : dim - 1;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int j = 16 * s + 8 * kgy + e;
+          const unsigned vj = (unsigned)(j - F) >> 31;           // 1 if j < F
+          const int cj = (int)vj * j + (1 - (int)vj) * (F - 1);  // clamped row
+          const unsigned keep = 0u - (vj & (unsigned)nvalid);    // all ones or zero
+          x[e] = __uint_as_float(__float_as_uint(zp[cj * dim + cn]) & keep);
+        }
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[s], pack_bf16x8(x), acc, 0, 0, 0);
+      }
       if (!nvalid) continue;
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const int i = 32 * I + 8 * (v >> 2) + 4 * kg + (v & 3);
-        if (i < F) {
+        const int io = 32 * I + 8 * (v >> 2) + 4 * kg + (v & 3);
+        if (io < F) {
           float val = acc[v];
-          if (i == 0) val += dR[b * dr_stride + n];
-          dZ[(b * F + i) * dim + n] = val;
+          if (io == 0) val += dR[b * dr_stride + n];
+          dZ[(b * F + io) * dim + n] = val;
         }
       }
     }
@@ -270,7 +308,7 @@ bool interaction_bf16_supported(int F, int dim) {
   if (!(KS == 1 || KS == 2 || KS == 4 || KS == 8)) return false;
   if (FB * KS > 32) return false;                       // register budget of the forward
   const int P = F * (F - 1) / 2;
-  return P * 4 <= 65536;
+  return (P + 1) * 4 <= 65536;
 }
 
 bool interaction_f32_supported(int F, int dim) {
@@ -324,14 +362,19 @@ hipError_t launch_interaction_bwd(const float* Z, const float* dR, int64_t dr_st
     return hipGetLastError();
   }
   const int FB = (F + 31) / 32;
-  int wpb = P > 0 ? 65536 / (P * 4) : 4;
+  int wpb = 65536 / ((P + 1) * 4);
   if (wpb > 4) wpb = 4;
   if (wpb < 1) wpb = 1;
-  const size_t lds = (size_t)wpb * (P > 0 ? P : 1) * sizeof(float);
+  const size_t lds = (size_t)wpb * (P + 1) * sizeof(float);
   const int64_t blocks = (batch + wpb - 1) / wpb;
+  const int KS = dim / 16;
   CTR_FB_DISPATCH(FB, {
-    interaction_bwd_mfma_kernel<FB><<<(unsigned)blocks, kThreads, lds, s>>>(
-        Z, dR, dr_stride, batch, F, dim, wpb, dZ);
+    switch (KS) {
+      case 1: interaction_bwd_mfma_kernel<FB, 1><<<(unsigned)blocks, kThreads, lds, s>>>(Z, dR, dr_stride, batch, F, wpb, dZ); break;
+      case 2: interaction_bwd_mfma_kernel<FB, 2><<<(unsigned)blocks, kThreads, lds, s>>>(Z, dR, dr_stride, batch, F, wpb, dZ); break;
+      case 4: interaction_bwd_mfma_kernel<FB, 4><<<(unsigned)blocks, kThreads, lds, s>>>(Z, dR, dr_stride, batch, F, wpb, dZ); break;
+      default: interaction_bwd_mfma_kernel<FB, 8><<<(unsigned)blocks, kThreads, lds, s>>>(Z, dR, dr_stride, batch, F, wpb, dZ); break;
+    }
   });
   return hipGetLastError();
 }

@@ -101,6 +101,18 @@ __device__ __forceinline__ int32_t key_after(const Src& S, int64_t q, int64_t n)
   return q + 1 < n ? S.key(q + 1) : -1;
 }
 
+// Where a finished row gradient goes besides row_grads: nowhere (MODE 0), or straight into
+// the sparse SGD update W[uniq[u]] -= lr * g[u] of an fp32 (MODE 1) or bf16 (MODE 2) table,
+// with the same arithmetic as the stand-alone update (one fused multiply-add, then
+// nearest-even for bf16).
+struct SgdTarget {
+  char* table;
+  int64_t total_rows;
+  int64_t row_bytes;
+  const int64_t* uniq;
+  float lr;
+};
+
 template <int G, int VPL>
 struct SegSmem {
   float first_row[kThreads / G][G * VPL * 4];
@@ -114,9 +126,9 @@ struct SegSmem {
 
 // One reduce-by-key level.  L0: entries are sorted positions of the occurrences (keys from
 // src, rows gathered from grad); otherwise entries are carries (keys may be -1 = empty).
-template <bool L0, int G, int VPL, typename Src>
+template <bool L0, int G, int VPL, int MODE, typename Src>
 __global__ __launch_bounds__(kThreads) void segreduce_kernel(
-    Src S, int64_t n, int dim, int64_t capacity, float* __restrict__ row_grads,
+    Src S, int64_t n, int dim, int64_t capacity, float* __restrict__ row_grads, SgdTarget sgd,
     int32_t* __restrict__ out_keys, float* __restrict__ out_rows) {
   constexpr int kSlots = kThreads / G;
   constexpr int kW = G * VPL * 4;              // floats per slot row in LDS
@@ -139,7 +151,35 @@ __global__ __launch_bounds__(kThreads) void segreduce_kernel(
     }
   };
   auto emit_complete = [&](int32_t u, const RowAcc<VPL>& r) {
-    if (u >= 0 && (int64_t)u < capacity) write_row(row_grads + (int64_t)u * dim, r);
+    if (u < 0 || (int64_t)u >= capacity) return;
+    if (row_grads) write_row(row_grads + (int64_t)u * dim, r);
+    if constexpr (MODE != 0) {
+      const int64_t key = sgd.uniq[u];
+      if (key < 0 || key >= sgd.total_rows) return;
+      char* wrow = sgd.table + key * sgd.row_bytes;
+#pragma unroll
+      for (int a = 0; a < VPL; ++a) {
+        const int c = col(a);
+        if (c >= dim) continue;
+        if constexpr (MODE == 1) {
+          float4* wp = reinterpret_cast<float4*>(wrow + (int64_t)c * 4);
+          const float4 w = *wp;
+          *wp = make_float4(__builtin_fmaf(-sgd.lr, r.v[a][0], w.x),
+                            __builtin_fmaf(-sgd.lr, r.v[a][1], w.y),
+                            __builtin_fmaf(-sgd.lr, r.v[a][2], w.z),
+                            __builtin_fmaf(-sgd.lr, r.v[a][3], w.w));
+        } else {
+          uint2* wp = reinterpret_cast<uint2*>(wrow + (int64_t)c * 2);
+          const uint2 w = *wp;
+          const float n0 = __builtin_fmaf(-sgd.lr, r.v[a][0], bf16_lo(w.x));
+          const float n1 = __builtin_fmaf(-sgd.lr, r.v[a][1], bf16_hi(w.x));
+          const float n2 = __builtin_fmaf(-sgd.lr, r.v[a][2], bf16_lo(w.y));
+          const float n3 = __builtin_fmaf(-sgd.lr, r.v[a][3], bf16_hi(w.y));
+          *wp = make_uint2(f32_to_bf16_bits(n0) | (f32_to_bf16_bits(n1) << 16),
+                           f32_to_bf16_bits(n2) | (f32_to_bf16_bits(n3) << 16));
+        }
+      }
+    }
   };
 
   int32_t fkey = -1, fcont = 0, lkey = -1;
@@ -358,6 +398,7 @@ BwdWs carve(void* base, int64_t n, int dim) {
 
 size_t embbag_bwd_workspace_bytes(int64_t nnz, int dim) { return carve(nullptr, nnz, dim).bytes; }
 
+
 #define CTR_SEG_DISPATCH(G_, VPL_, ...)                                     \
   do {                                                                      \
     switch (G_) {                                                           \
@@ -375,43 +416,60 @@ size_t embbag_bwd_workspace_bytes(int64_t nnz, int dim) { return carve(nullptr, 
     }                                                                       \
   } while (0)
 
-hipError_t launch_embbag_bwd(const float* grad, int64_t sb, int64_t st, const int64_t* offsets,
-                             int64_t batch, int32_t num_tables, int dim, int64_t nnz,
-                             const int32_t* perm, const int32_t* inverse,
-                             const int32_t* num_unique, float* row_grads, void* workspace,
-                             hipStream_t s) {
-  (void)num_unique;
-  if (nnz == 0) return hipSuccess;
-  BwdWs w = carve(workspace, nnz, dim);
-  const int64_t num_bags = (int64_t)num_tables * batch;
-
-  {
-    const int64_t waves = (num_bags + 63) / 64;
-    const int64_t blocks = (waves + 3) / 4;
-    bag_of_kernel<<<(unsigned)blocks, kThreads, 0, s>>>(offsets, num_bags, nnz, w.bag_of);
-  }
-  seg_src_kernel<<<(unsigned)((nnz + kThreads - 1) / kThreads), kThreads, 0, s>>>(
-      perm, inverse, w.bag_of, nnz, w.src);
-
+template <int MODE>
+static void segreduce_levels(const L0Source& s0, int64_t nnz, int dim, float* row_grads,
+                             const SgdTarget& sgd, BwdWs& w, hipStream_t s) {
   const RowGeom rg = row_geom(dim / 4);
   const int64_t chunk = chunk_positions(dim);
   CTR_SEG_DISPATCH(rg.G, rg.VPL, {
     int64_t len = nnz;
     int64_t blocks = (len + chunk - 1) / chunk;
     int cur = 0;
-    L0Source s0{w.src, grad, sb, st, batch, num_bags};
-    segreduce_kernel<true, G, VPL, L0Source><<<(unsigned)blocks, kThreads, 0, s>>>(
-        s0, len, dim, nnz, row_grads, blocks > 1 ? w.ckeys[cur] : nullptr, w.crows[cur]);
+    segreduce_kernel<true, G, VPL, MODE, L0Source><<<(unsigned)blocks, kThreads, 0, s>>>(
+        s0, len, dim, nnz, row_grads, sgd, blocks > 1 ? w.ckeys[cur] : nullptr, w.crows[cur]);
     while (blocks > 1) {
       len = 2 * blocks;
       blocks = (len + chunk - 1) / chunk;
       LnSource sn{w.ckeys[cur], w.crows[cur], dim};
-      segreduce_kernel<false, G, VPL, LnSource><<<(unsigned)blocks, kThreads, 0, s>>>(
-          sn, len, dim, nnz, row_grads, blocks > 1 ? w.ckeys[cur ^ 1] : nullptr,
+      segreduce_kernel<false, G, VPL, MODE, LnSource><<<(unsigned)blocks, kThreads, 0, s>>>(
+          sn, len, dim, nnz, row_grads, sgd, blocks > 1 ? w.ckeys[cur ^ 1] : nullptr,
           w.crows[cur ^ 1]);
       cur ^= 1;
     }
   });
+}
+
+hipError_t launch_embbag_bwd(const float* grad, int64_t sb, int64_t st, const int64_t* offsets,
+                             int64_t batch, int32_t num_tables, int dim, int64_t nnz,
+                             const int32_t* perm, const int32_t* inverse, const int2* sorted_src,
+                             const int32_t* num_unique, float* row_grads, void* table,
+                             int sgd_mode, int64_t total_rows, const int64_t* uniq, float lr,
+                             void* workspace, hipStream_t s) {
+  (void)num_unique;
+  if (nnz == 0) return hipSuccess;
+  BwdWs w = carve(workspace, nnz, dim);
+  const int64_t num_bags = (int64_t)num_tables * batch;
+
+  const int2* src = sorted_src;
+  if (!src) {
+    // (u, bag) per sorted position from perm and inverse: expand the bags, then gather.
+    const int64_t waves = (num_bags + 63) / 64;
+    const int64_t blocks = (waves + 3) / 4;
+    bag_of_kernel<<<(unsigned)blocks, kThreads, 0, s>>>(offsets, num_bags, nnz, w.bag_of);
+    seg_src_kernel<<<(unsigned)((nnz + kThreads - 1) / kThreads), kThreads, 0, s>>>(
+        perm, inverse, w.bag_of, nnz, w.src);
+    src = w.src;
+  }
+
+  L0Source s0{src, grad, sb, st, batch, num_bags};
+  SgdTarget sgd{static_cast<char*>(table), total_rows,
+                (int64_t)dim * (sgd_mode == 2 ? 2 : 4), uniq, lr};
+  if (sgd_mode == 1)
+    segreduce_levels<1>(s0, nnz, dim, row_grads, sgd, w, s);
+  else if (sgd_mode == 2)
+    segreduce_levels<2>(s0, nnz, dim, row_grads, sgd, w, s);
+  else
+    segreduce_levels<0>(s0, nnz, dim, row_grads, sgd, w, s);
   return hipGetLastError();
 }
 

@@ -3,13 +3,22 @@
 //
 // Method: "How TensorNet Supercharges Sparse Feature Training on TensorFlow", section
 // "Core Optimizations": collect the batch's IDs, sort them and give each distinct ID a
-// contiguous index.  The sort is ours: reduce-then-scan LSD radix with 8-bit digits.
+// contiguous index.  The sort is ours: reduce-then-scan LSD radix, digits of up to 8 bits
+// spread evenly over the passes (a 28-bit row key takes four 7-bit passes: with 2048-key
+// tiles, wider digits leave too few keys per digit for the output runs to coalesce):
+//   keys      one wave per 64 bags forms the keys of their occurrences (the bag of each
+//             occurrence comes from a shuffle binary search over the 64 bag ends, so the
+//             table and the bag are known without a search over all offsets)
 //   upsweep   each block counts digits of its contiguous range (wave-aggregated counts)
 //   scan      one block per digit scans that digit's per-block counts
-//   downsweep each block ranks its tiles stably with wave64 ballot "multisplit"
-//             (eight ballots give the mask of lanes holding the same digit), stages the
-//             tile in LDS in digit order and writes it out in runs per digit.
-// No inter-block waiting anywhere: every kernel only reads what earlier launches wrote.
+//   downsweep each block ranks its tiles stably with wave64 ballot "multisplit" (one
+//             ballot per digit bit gives the mask of lanes holding the same digit), stages
+//             the tile in LDS in digit order and writes it out in runs per digit.
+// The payload is the occurrence index and, when bags are given, the occurrence's bag, so
+// that the finalize can emit (distinct-row index, bag) per sorted position for the
+// backward's reduce-by-key.  No inter-block waiting anywhere.
+#include <utility>
+
 #include "ctr_internal.h"
 
 namespace ctr {
@@ -18,10 +27,9 @@ namespace {
 constexpr int kThreads = 256;                 // 4 waves
 constexpr int kItems = 8;                     // keys per thread per tile
 constexpr int kTile = kThreads * kItems;      // 2048 keys per tile
-constexpr int kBuckets = 256;                 // 8-bit digits
+constexpr int kMaxBits = 8;                   // widest digit (wider digits scatter worse)
 constexpr int kMaxBlocks = 1024;              // radix blocks (ranges) per pass
 constexpr int kFinTile = 2048;                // positions per finalize block
-constexpr int kMaxTablesLds = 4096;
 
 __device__ __forceinline__ uint64_t lanemask_lt() {
   const int lane = threadIdx.x & 63;
@@ -64,64 +72,91 @@ __device__ __forceinline__ uint32_t block_excl_scan_256(uint32_t v, uint32_t* tm
   return base + x - v;
 }
 
-// --------------------------------------------------------------------------- a1: keys
-// key = row_base[t] + (modulus ? floor_mod(id, modulus) : id), XOR `flip` to make the
-// signed order an unsigned one when the full 64-bit range is sorted.
-template <bool ID64>
-__global__ __launch_bounds__(kThreads) void form_keys_kernel(
-    const void* __restrict__ ids, int64_t n, const int64_t* __restrict__ offsets, int64_t batch,
-    int32_t num_tables, const int64_t* __restrict__ row_base, int64_t modulus, uint64_t flip,
-    uint64_t* __restrict__ keys) {
-  __shared__ int64_t tb[kMaxTablesLds + 1];
-  const bool tables = row_base != nullptr;
-  if (tables) {
-    for (int t = threadIdx.x; t <= num_tables; t += kThreads)
-      tb[t] = offsets[(int64_t)t * batch];
-    __syncthreads();
+__device__ __forceinline__ int64_t floor_mod(int64_t id, int64_t m) {
+  if (m > 0) {
+    id %= m;
+    if (id < 0) id += m;
   }
+  return id;
+}
+
+// --------------------------------------------------------------------------- a1: keys
+// Bags known: one wave per 64 consecutive bags; lane l holds the end of bag s0 + l and every
+// occurrence finds its bag by a 6-step binary search over those ends (shuffles).
+// `parts` waves share one group of 64 bags, each taking every parts-th stretch of 64
+// occurrences, so long bags still spread over enough waves to fill the chip.
+template <bool ID64>
+__global__ __launch_bounds__(kThreads) void form_keys_bags_kernel(
+    const void* __restrict__ ids, int64_t n, const int64_t* __restrict__ offsets, int64_t batch,
+    int64_t num_bags, const int64_t* __restrict__ row_base, int64_t modulus, uint64_t flip,
+    int parts, uint64_t* __restrict__ keys, uint32_t* __restrict__ bags) {
+  const int lane = threadIdx.x & 63;
+  const int64_t wave = ((int64_t)blockIdx.x * kThreads + threadIdx.x) >> 6;
+  const int64_t s0 = (wave / parts) * 64;
+  const int part = (int)(wave % parts);
+  if (s0 >= num_bags) return;
+  const int64_t s = s0 + lane;
+  const int64_t my_end = s < num_bags ? clamp64(offsets[s + 1], 0, n) : INT64_MAX;
+  const int64_t beg = clamp64(offsets[s0], 0, n);
+  const int64_t last = s0 + 64 < num_bags ? s0 + 64 : num_bags;
+  const int64_t end = clamp64(offsets[last], beg, n);
+  for (int64_t i0 = beg + (int64_t)part * 64; i0 < end; i0 += (int64_t)parts * 64) {
+    const int64_t i = i0 + lane;
+    int l = 0;
+#pragma unroll
+    for (int step = 32; step > 0; step >>= 1) {
+      const int64_t e = __shfl(my_end, l + step - 1, 64);
+      if (e <= i) l += step;
+    }
+    if (i < end) {
+      const int64_t bag = s0 + l;
+      const int64_t id = ID64 ? static_cast<const int64_t*>(ids)[i]
+                              : (int64_t) static_cast<const int32_t*>(ids)[i];
+      int64_t key = floor_mod(id, modulus);
+      if (row_base) key += row_base[bag / batch];
+      keys[i] = (uint64_t)key ^ flip;
+      bags[i] = (uint32_t)bag;
+    }
+  }
+}
+
+// No bags: each occurrence is its own bag.
+template <bool ID64>
+__global__ __launch_bounds__(kThreads) void form_keys_flat_kernel(const void* __restrict__ ids,
+                                                                  int64_t n, int64_t modulus,
+                                                                  uint64_t flip,
+                                                                  uint64_t* __restrict__ keys) {
   const int64_t stride = (int64_t)gridDim.x * kThreads;
   for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n; i += stride) {
-    int64_t id = ID64 ? static_cast<const int64_t*>(ids)[i]
-                      : (int64_t) static_cast<const int32_t*>(ids)[i];
-    if (modulus > 0) {
-      id %= modulus;
-      if (id < 0) id += modulus;
-    }
-    int64_t key = id;
-    if (tables) {
-      int lo = 0, hi = num_tables - 1;      // last t with tb[t] <= i
-      while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (tb[mid] <= i) lo = mid; else hi = mid - 1;
-      }
-      key += row_base[lo];
-    }
-    keys[i] = (uint64_t)key ^ flip;
+    const int64_t id = ID64 ? static_cast<const int64_t*>(ids)[i]
+                            : (int64_t) static_cast<const int32_t*>(ids)[i];
+    keys[i] = (uint64_t)floor_mod(id, modulus) ^ flip;
   }
 }
 
 // --------------------------------------------------------------------------- upsweep
+template <int NB>
 __global__ __launch_bounds__(kThreads) void radix_upsweep_kernel(
     const uint64_t* __restrict__ keys, int64_t n, int shift, int nbits, int64_t per_block,
     uint32_t* __restrict__ hist, int nblocks) {
-  __shared__ uint32_t cnt[4][kBuckets];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  for (int i = threadIdx.x; i < 4 * kBuckets; i += kThreads) (&cnt[0][0])[i] = 0;
+  __shared__ uint32_t cnt[4][NB];
+  const int wave = threadIdx.x >> 6;
+  for (int i = threadIdx.x; i < 4 * NB; i += kThreads) (&cnt[0][0])[i] = 0;
   __syncthreads();
   const uint32_t mask = (1u << nbits) - 1u;
   const int64_t beg = (int64_t)blockIdx.x * per_block;
   const int64_t end = beg + per_block < n ? beg + per_block : n;
+  const uint64_t lt = lanemask_lt();
   for (int64_t base = beg; base < end; base += kThreads) {
     const int64_t e = base + threadIdx.x;
     const bool valid = e < end;
     const uint32_t d = valid ? (uint32_t)(keys[e] >> shift) & mask : 0u;
     const uint64_t active = __ballot(valid);
     const uint64_t m = match_digit(d, nbits, active);
-    if (valid && (m & lanemask_lt()) == 0) cnt[wave][d] += (uint32_t)__popcll(m);
-    (void)lane;
+    if (valid && (m & lt) == 0) cnt[wave][d] += (uint32_t)__popcll(m);
   }
   __syncthreads();
-  for (int d = threadIdx.x; d < kBuckets; d += kThreads)
+  for (int d = threadIdx.x; d < NB; d += kThreads)
     hist[(int64_t)d * nblocks + blockIdx.x] = cnt[0][d] + cnt[1][d] + cnt[2][d] + cnt[3][d];
 }
 
@@ -152,32 +187,60 @@ __global__ __launch_bounds__(kThreads) void radix_scan_kernel(uint32_t* __restri
 }
 
 // --------------------------------------------------------------------------- downsweep
+template <int NB>
 struct DownsweepSmem {
   uint64_t keys[kTile];
   uint32_t vals[kTile];
-  uint32_t wcnt[4][kBuckets];
-  uint32_t run[kBuckets];
-  uint32_t tstart[kBuckets];
-  uint32_t tcount[kBuckets];
+  uint32_t bags[kTile];
+  uint32_t wcnt[4][NB];
+  uint32_t run[NB];
+  uint32_t tstart[NB];
+  uint32_t tcount[NB];
   uint32_t tmp[4];
 };
 
-template <bool IDENTITY>
+// Exclusive scan over NB per-digit values held in LDS `a` (in place); returns nothing,
+// every thread must call it.  Thread t owns digits [t*DPT, (t+1)*DPT).
+template <int NB>
+__device__ __forceinline__ void lds_excl_scan(uint32_t* a, uint32_t* tmp) {
+  constexpr int DPT = NB / kThreads;
+  uint32_t v[DPT];
+  uint32_t s = 0;
+#pragma unroll
+  for (int j = 0; j < DPT; ++j) {
+    v[j] = a[threadIdx.x * DPT + j];
+    s += v[j];
+  }
+  uint32_t total;
+  uint32_t run = block_excl_scan_256(s, tmp, &total);
+#pragma unroll
+  for (int j = 0; j < DPT; ++j) {
+    a[threadIdx.x * DPT + j] = run;
+    run += v[j];
+  }
+}
+
+// IDENT: payload of pass 0 is the element index.  BAGS: a second payload (the bag) rides along.
+template <int NB, bool IDENT, bool BAGS>
 __global__ __launch_bounds__(kThreads) void radix_downsweep_kernel(
     const uint64_t* __restrict__ keys_in, const uint32_t* __restrict__ vals_in,
-    uint64_t* __restrict__ keys_out, uint32_t* __restrict__ vals_out, int64_t n, int shift,
+    const uint32_t* __restrict__ bags_in, uint64_t* __restrict__ keys_out,
+    uint32_t* __restrict__ vals_out, uint32_t* __restrict__ bags_out, int64_t n, int shift,
     int nbits, int64_t per_block, const uint32_t* __restrict__ hist,
     const uint32_t* __restrict__ totals, int nblocks) {
-  __shared__ DownsweepSmem sm;
+  __shared__ DownsweepSmem<NB> sm;
+  constexpr int DPT = NB / kThreads;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const uint32_t mask = (1u << nbits) - 1u;
 
   // Global start of each digit for this block: digits before it, then blocks before it.
-  {
-    const uint32_t tot = totals[threadIdx.x];
-    uint32_t all;
-    const uint32_t excl = block_excl_scan_256(tot, sm.tmp, &all);
-    sm.run[threadIdx.x] = excl + hist[(int64_t)threadIdx.x * nblocks + blockIdx.x];
+  for (int j = 0; j < DPT; ++j) sm.run[threadIdx.x * DPT + j] = totals[threadIdx.x * DPT + j];
+  __syncthreads();
+  lds_excl_scan<NB>(sm.run, sm.tmp);
+  __syncthreads();
+  for (int j = 0; j < DPT; ++j) {
+    const int d = threadIdx.x * DPT + j;
+    sm.run[d] += hist[(int64_t)d * nblocks + blockIdx.x];
   }
   __syncthreads();
 
@@ -188,6 +251,7 @@ __global__ __launch_bounds__(kThreads) void radix_downsweep_kernel(
   for (int64_t tile = beg; tile < end; tile += kTile) {
     uint64_t key[kItems];
     uint32_t val[kItems];
+    uint32_t bag[kItems];
     uint32_t rank[kItems];
     bool valid[kItems];
 #pragma unroll
@@ -195,9 +259,10 @@ __global__ __launch_bounds__(kThreads) void radix_downsweep_kernel(
       const int64_t e = tile + (int64_t)wave * 64 * kItems + k * 64 + lane;
       valid[k] = e < end;
       key[k] = valid[k] ? keys_in[e] : 0ull;
-      val[k] = valid[k] ? (IDENTITY ? (uint32_t)e : vals_in[e]) : 0u;
+      val[k] = valid[k] ? (IDENT ? (uint32_t)e : vals_in[e]) : 0u;
+      bag[k] = (BAGS && valid[k]) ? bags_in[e] : 0u;
     }
-    for (int d = lane; d < kBuckets; d += 64) sm.wcnt[wave][d] = 0;
+    for (int d = lane; d < NB; d += 64) sm.wcnt[wave][d] = 0;
     __builtin_amdgcn_wave_barrier();
 #pragma unroll
     for (int k = 0; k < kItems; ++k) {
@@ -213,19 +278,20 @@ __global__ __launch_bounds__(kThreads) void radix_downsweep_kernel(
       rank[k] = pre + r;
     }
     __syncthreads();
-    {
-      const int d = threadIdx.x;
+#pragma unroll
+    for (int j = 0; j < DPT; ++j) {
+      const int d = threadIdx.x * DPT + j;
       const uint32_t c0 = sm.wcnt[0][d], c1 = sm.wcnt[1][d], c2 = sm.wcnt[2][d],
                      c3 = sm.wcnt[3][d];
       sm.wcnt[0][d] = 0;
       sm.wcnt[1][d] = c0;
       sm.wcnt[2][d] = c0 + c1;
       sm.wcnt[3][d] = c0 + c1 + c2;
-      const uint32_t cnt = c0 + c1 + c2 + c3;
-      sm.tcount[d] = cnt;
-      uint32_t all;
-      sm.tstart[d] = block_excl_scan_256(cnt, sm.tmp, &all);
+      sm.tcount[d] = c0 + c1 + c2 + c3;
+      sm.tstart[d] = c0 + c1 + c2 + c3;
     }
+    __syncthreads();
+    lds_excl_scan<NB>(sm.tstart, sm.tmp);
     __syncthreads();
 #pragma unroll
     for (int k = 0; k < kItems; ++k) {
@@ -234,6 +300,7 @@ __global__ __launch_bounds__(kThreads) void radix_downsweep_kernel(
         const uint32_t pos = sm.tstart[d] + sm.wcnt[wave][d] + rank[k];
         sm.keys[pos] = key[k];
         sm.vals[pos] = val[k];
+        if (BAGS) sm.bags[pos] = bag[k];
       }
     }
     __syncthreads();
@@ -244,27 +311,44 @@ __global__ __launch_bounds__(kThreads) void radix_downsweep_kernel(
       const uint32_t o = sm.run[d] + (uint32_t)q - sm.tstart[d];
       keys_out[o] = kk;
       vals_out[o] = sm.vals[q];
+      if (BAGS) bags_out[o] = sm.bags[q];
     }
     __syncthreads();
-    sm.run[threadIdx.x] += sm.tcount[threadIdx.x];
+#pragma unroll
+    for (int j = 0; j < DPT; ++j) sm.run[threadIdx.x * DPT + j] += sm.tcount[threadIdx.x * DPT + j];
     __syncthreads();
   }
 }
 
 // --------------------------------------------------------------------------- finalize
+// Positions are striped: in round j a 256-thread block covers 256 consecutive positions, so
+// every load and store is coalesced; a head is a position whose key differs from the one
+// before, and ranks come from wave ballots (popcount of the heads before a lane).
+constexpr int kFinRounds = kFinTile / kThreads;     // 8
+
+__device__ __forceinline__ bool is_head(const uint64_t* __restrict__ sk, int64_t p, int64_t n,
+                                        uint64_t* key) {
+  if (p >= n) return false;
+  *key = sk[p];
+  return p == 0 || *key != sk[p - 1];
+}
+
 __global__ __launch_bounds__(kThreads) void heads_count_kernel(const uint64_t* __restrict__ sk,
                                                                int64_t n,
                                                                uint32_t* __restrict__ tile_heads) {
-  __shared__ uint32_t tmp[4];
+  __shared__ uint32_t wsum[4];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t t0 = (int64_t)blockIdx.x * kFinTile;
   uint32_t c = 0;
-  for (int j = 0; j < kFinTile / kThreads; ++j) {
-    const int64_t p = t0 + (int64_t)j * kThreads + threadIdx.x;
-    if (p < n) c += (p == 0 || sk[p] != sk[p - 1]) ? 1u : 0u;
+#pragma unroll
+  for (int j = 0; j < kFinRounds; ++j) {
+    uint64_t k;
+    const bool h = is_head(sk, t0 + (int64_t)j * kThreads + threadIdx.x, n, &k);
+    c += (uint32_t)__popcll(__ballot(h));
   }
-  uint32_t total;
-  block_excl_scan_256(c, tmp, &total);
-  if (threadIdx.x == 0) tile_heads[blockIdx.x] = total;
+  if (lane == 0) wsum[wave] = c;
+  __syncthreads();
+  if (threadIdx.x == 0) tile_heads[blockIdx.x] = wsum[0] + wsum[1] + wsum[2] + wsum[3];
 }
 
 // One block of 1024 threads: exclusive scan of the per-tile head counts; publishes U.
@@ -304,39 +388,41 @@ __global__ __launch_bounds__(1024) void heads_scan_kernel(uint32_t* __restrict__
   }
 }
 
+// sorted_src[p] = (distinct-row index of position p, bag of its occurrence); without bags
+// the occurrence is its own bag.
 __global__ __launch_bounds__(kThreads) void unique_finalize_kernel(
-    const uint64_t* __restrict__ sk, const uint32_t* __restrict__ sv, int64_t n, uint64_t flip,
+    const uint64_t* __restrict__ sk, const uint32_t* __restrict__ sv,
+    const uint32_t* __restrict__ sbag, int64_t n, uint64_t flip,
     const uint32_t* __restrict__ tile_heads, int64_t* __restrict__ uniq,
-    int32_t* __restrict__ inverse, int32_t* __restrict__ seg_offsets) {
-  __shared__ uint32_t tmp[4];
-  constexpr int kPer = kFinTile / kThreads;     // 8 consecutive positions per thread
-  const int64_t p0 = (int64_t)blockIdx.x * kFinTile + (int64_t)threadIdx.x * kPer;
-  uint64_t k[kPer];
-  bool head[kPer];
-  uint32_t c = 0;
-  uint64_t prev = (p0 > 0 && p0 <= n) ? sk[p0 - 1] : 0ull;
-#pragma unroll
-  for (int j = 0; j < kPer; ++j) {
-    const int64_t p = p0 + j;
-    k[j] = p < n ? sk[p] : 0ull;
-    head[j] = p < n && (p == 0 || k[j] != prev);
-    prev = k[j];
-    c += head[j] ? 1u : 0u;
-  }
-  uint32_t total;
-  uint32_t run = tile_heads[blockIdx.x] + block_excl_scan_256(c, tmp, &total);
-#pragma unroll
-  for (int j = 0; j < kPer; ++j) {
-    const int64_t p = p0 + j;
-    if (p >= n) break;
-    if (head[j]) ++run;
-    const uint32_t r = run - 1u;
-    if (head[j]) {
-      uniq[r] = (int64_t)(k[j] ^ flip);
-      if (seg_offsets) seg_offsets[r] = (int32_t)p;
+    int32_t* __restrict__ inverse, int32_t* __restrict__ seg_offsets,
+    int2* __restrict__ sorted_src) {
+  __shared__ uint32_t wsum[4];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const uint64_t le = (lane == 63) ? ~0ull : ((2ull << lane) - 1ull);
+  const int64_t t0 = (int64_t)blockIdx.x * kFinTile;
+  uint32_t base = tile_heads[blockIdx.x];         // heads before this tile
+  for (int j = 0; j < kFinRounds; ++j) {
+    const int64_t p = t0 + (int64_t)j * kThreads + threadIdx.x;
+    uint64_t k = 0;
+    const bool h = is_head(sk, p, n, &k);
+    const uint64_t m = __ballot(h);
+    if (lane == 0) wsum[wave] = (uint32_t)__popcll(m);
+    __syncthreads();
+    uint32_t before = base;
+    for (int w = 0; w < wave; ++w) before += wsum[w];
+    const uint32_t total = wsum[0] + wsum[1] + wsum[2] + wsum[3];
+    __syncthreads();
+    if (p < n) {
+      const uint32_t r = before + (uint32_t)__popcll(m & le) - 1u;   // heads <= p, minus one
+      if (h) {
+        uniq[r] = (int64_t)(k ^ flip);
+        if (seg_offsets) seg_offsets[r] = (int32_t)p;
+      }
+      const uint32_t occ = sv[p];
+      if (occ < (uint64_t)n) inverse[occ] = (int32_t)r;
+      if (sorted_src) sorted_src[p] = make_int2((int32_t)r, (int32_t)(sbag ? sbag[p] : occ));
     }
-    const uint32_t occ = sv[p];
-    if (occ < (uint64_t)n) inverse[occ] = (int32_t)r;
+    base += total;
   }
 }
 
@@ -354,6 +440,8 @@ struct UniqueWs {
   uint64_t* keys_b;
   uint32_t* vals_a;
   uint32_t* vals_b;
+  uint32_t* bags_a;
+  uint32_t* bags_b;
   uint32_t* hist;
   uint32_t* totals;
   uint32_t* tile_heads;
@@ -373,49 +461,93 @@ UniqueWs carve(void* base, int64_t n) {
   w.keys_b = reinterpret_cast<uint64_t*>(take(sizeof(uint64_t) * (size_t)n));
   w.vals_a = reinterpret_cast<uint32_t*>(take(sizeof(uint32_t) * (size_t)n));
   w.vals_b = reinterpret_cast<uint32_t*>(take(sizeof(uint32_t) * (size_t)n));
-  w.hist = reinterpret_cast<uint32_t*>(take(sizeof(uint32_t) * kBuckets * kMaxBlocks));
-  w.totals = reinterpret_cast<uint32_t*>(take(sizeof(uint32_t) * kBuckets));
-  w.tile_heads =
-      reinterpret_cast<uint32_t*>(take(sizeof(uint32_t) * (size_t)((n + kFinTile - 1) / kFinTile + 1)));
+  w.bags_a = reinterpret_cast<uint32_t*>(take(sizeof(uint32_t) * (size_t)n));
+  w.bags_b = reinterpret_cast<uint32_t*>(take(sizeof(uint32_t) * (size_t)n));
+  w.hist = reinterpret_cast<uint32_t*>(take(sizeof(uint32_t) * (1 << kMaxBits) * kMaxBlocks));
+  w.totals = reinterpret_cast<uint32_t*>(take(sizeof(uint32_t) * (1 << kMaxBits)));
+  w.tile_heads = reinterpret_cast<uint32_t*>(
+      take(sizeof(uint32_t) * (size_t)((n + kFinTile - 1) / kFinTile + 1)));
   w.bytes = off;
   return w;
 }
 
+template <int NB>
+void radix_pass(bool first, bool bags, const uint64_t* kin, const uint32_t* vin,
+                const uint32_t* bin, uint64_t* kout, uint32_t* vout, uint32_t* bout, int64_t n,
+                int shift, int nbits, int64_t per_block, uint32_t* hist, uint32_t* totals,
+                int nblocks, hipStream_t s) {
+  radix_upsweep_kernel<NB><<<nblocks, kThreads, 0, s>>>(kin, n, shift, nbits, per_block, hist,
+                                                        nblocks);
+  radix_scan_kernel<<<NB, kThreads, 0, s>>>(hist, nblocks, totals);
+#define CTR_DS(I, B)                                                                         \
+  radix_downsweep_kernel<NB, I, B><<<nblocks, kThreads, 0, s>>>(kin, vin, bin, kout, vout,   \
+                                                                bout, n, shift, nbits,       \
+                                                                per_block, hist, totals,     \
+                                                                nblocks)
+  if (first) {
+    if (bags) CTR_DS(true, true); else CTR_DS(true, false);
+  } else {
+    if (bags) CTR_DS(false, true); else CTR_DS(false, false);
+  }
+#undef CTR_DS
+}
+
 }  // namespace
 
-size_t unique_workspace_bytes(int64_t n, bool /*need_perm*/) { return carve(nullptr, n).bytes; }
+size_t unique_workspace_bytes(int64_t n) { return carve(nullptr, n).bytes; }
 
 hipError_t launch_unique(const void* ids, bool ids64, int64_t n, const int64_t* offsets,
                          int64_t batch, int32_t num_tables, const int64_t* row_base,
                          int64_t modulus, int key_bits, bool key_signed, int64_t* uniq,
                          int32_t* inverse, int32_t* num_unique, int32_t* perm,
-                         int32_t* seg_offsets, void* workspace, hipStream_t s) {
+                         int32_t* seg_offsets, int2* sorted_src, void* workspace,
+                         hipStream_t s) {
   if (n == 0) {
     unique_empty_kernel<<<1, 64, 0, s>>>(num_unique, seg_offsets);
     return hipGetLastError();
   }
   UniqueWs w = carve(workspace, n);
   const uint64_t flip = key_signed ? (1ull << 63) : 0ull;
+  const bool bags = offsets != nullptr && sorted_src != nullptr;
 
-  // a1: keys
-  {
+  // a1: keys (and bags)
+  if (offsets) {
+    const int64_t num_bags = (int64_t)num_tables * batch;
+    const int64_t groups = (num_bags + 63) / 64;
+    // about 4096 waves, but no part shorter than one 64-occurrence stretch
+    int64_t parts = (4096 + groups - 1) / groups;
+    const int64_t stretches = (n / (groups > 0 ? groups : 1) + 63) / 64;
+    if (parts > stretches) parts = stretches;
+    if (parts < 1) parts = 1;
+    const int64_t blocks = (groups * parts + 3) / 4;
+    if (blocks > 0) {
+      if (ids64)
+        form_keys_bags_kernel<true><<<(unsigned)blocks, kThreads, 0, s>>>(
+            ids, n, offsets, batch, num_bags, row_base, modulus, flip, (int)parts, w.keys_a,
+            w.bags_a);
+      else
+        form_keys_bags_kernel<false><<<(unsigned)blocks, kThreads, 0, s>>>(
+            ids, n, offsets, batch, num_bags, row_base, modulus, flip, (int)parts, w.keys_a,
+            w.bags_a);
+    }
+  } else {
     int64_t blocks = (n + kThreads - 1) / kThreads;
     if (blocks > 8192) blocks = 8192;
     if (ids64)
-      form_keys_kernel<true><<<(unsigned)blocks, kThreads, 0, s>>>(
-          ids, n, offsets, batch, num_tables, row_base, modulus, flip, w.keys_a);
+      form_keys_flat_kernel<true><<<(unsigned)blocks, kThreads, 0, s>>>(ids, n, modulus, flip,
+                                                                        w.keys_a);
     else
-      form_keys_kernel<false><<<(unsigned)blocks, kThreads, 0, s>>>(
-          ids, n, offsets, batch, num_tables, row_base, modulus, flip, w.keys_a);
+      form_keys_flat_kernel<false><<<(unsigned)blocks, kThreads, 0, s>>>(ids, n, modulus, flip,
+                                                                         w.keys_a);
   }
 
-  // a2: stable LSD radix sort of (key, occurrence) over the live key bits
+  // a2: stable LSD radix sort of (key, occurrence[, bag]) over the live key bits
   const int64_t ntiles = (n + kTile - 1) / kTile;
   int nblocks = (int)(ntiles < kMaxBlocks ? ntiles : kMaxBlocks);
   const int64_t tiles_per_block = (ntiles + nblocks - 1) / nblocks;
   nblocks = (int)((ntiles + tiles_per_block - 1) / tiles_per_block);
   const int64_t per_block = tiles_per_block * kTile;
-  const int passes = (key_bits + 7) / 8;
+  const int passes = (key_bits + kMaxBits - 1) / kMaxBits;
 
   uint64_t* kin = w.keys_a;
   uint64_t* kout = w.keys_b;
@@ -429,33 +561,31 @@ hipError_t launch_unique(const void* ids, bool ids64, int64_t n, const int64_t* 
     vbuf[1] = w.vals_b;
   }
   const uint32_t* vin = nullptr;
+  uint32_t* bin = w.bags_a;
+  uint32_t* bout = w.bags_b;
+  int shift = 0;
   for (int p = 0; p < passes; ++p) {
-    const int shift = 8 * p;
-    const int nbits = (key_bits - shift) < 8 ? (key_bits - shift) : 8;
+    const int left = key_bits - shift;
+    const int nbits = (left + (passes - p) - 1) / (passes - p);   // spread bits evenly
     uint32_t* vout = vbuf[(passes - 1 - p) & 1];
-    radix_upsweep_kernel<<<nblocks, kThreads, 0, s>>>(kin, n, shift, nbits, per_block, w.hist,
-                                                      nblocks);
-    radix_scan_kernel<<<kBuckets, kThreads, 0, s>>>(w.hist, nblocks, w.totals);
-    if (p == 0)
-      radix_downsweep_kernel<true><<<nblocks, kThreads, 0, s>>>(
-          kin, nullptr, kout, vout, n, shift, nbits, per_block, w.hist, w.totals, nblocks);
-    else
-      radix_downsweep_kernel<false><<<nblocks, kThreads, 0, s>>>(
-          kin, vin, kout, vout, n, shift, nbits, per_block, w.hist, w.totals, nblocks);
+    radix_pass<256>(p == 0, bags, kin, vin, bin, kout, vout, bout, n, shift, nbits, per_block,
+                    w.hist, w.totals, nblocks, s);
+    shift += nbits;
     vin = vout;
-    uint64_t* t = kin;
-    kin = kout;
-    kout = t;
+    std::swap(kin, kout);
+    std::swap(bin, bout);
   }
   const uint64_t* sk = kin;
   const uint32_t* sv = vin;
+  const uint32_t* sb = bags ? bin : nullptr;
 
-  // finalize: heads, their scan, and the scatter of uniq / seg / inverse
+  // finalize: heads, their scan, and the scatter of uniq / seg / inverse / sorted_src
   const int64_t ftiles = (n + kFinTile - 1) / kFinTile;
   heads_count_kernel<<<(unsigned)ftiles, kThreads, 0, s>>>(sk, n, w.tile_heads);
   heads_scan_kernel<<<1, 1024, 0, s>>>(w.tile_heads, ftiles, n, num_unique, seg_offsets);
-  unique_finalize_kernel<<<(unsigned)ftiles, kThreads, 0, s>>>(sk, sv, n, flip, w.tile_heads,
-                                                               uniq, inverse, seg_offsets);
+  unique_finalize_kernel<<<(unsigned)ftiles, kThreads, 0, s>>>(sk, sv, sb, n, flip, w.tile_heads,
+                                                               uniq, inverse, seg_offsets,
+                                                               sorted_src);
   return hipGetLastError();
 }
 

@@ -21,7 +21,8 @@ CTR_I32, CTR_I64 = 0, 1
 
 EXPORTED = [
     "ctr_version", "ctr_status_string", "ctr_last_error", "ctr_unique_ids", "ctr_gather_rows",
-    "ctr_embbag_fwd", "ctr_embbag_bwd", "ctr_sparse_sgd", "ctr_dot_interaction_fwd",
+    "ctr_embbag_fwd", "ctr_embbag_bwd", "ctr_embbag_bwd_sgd", "ctr_sparse_sgd",
+    "ctr_dot_interaction_fwd",
     "ctr_dot_interaction_bwd", "ctr_init_table_hash", "ctr_validate_csr",
 ]
 
@@ -54,10 +55,12 @@ def load() -> ctypes.CDLL:
         "ctr_version": (i32, []),
         "ctr_status_string": (ctypes.c_char_p, [i32]),
         "ctr_last_error": (ctypes.c_char_p, []),
-        "ctr_unique_ids": (i32, [P, i32, i64, P, i64, i32, P, i64, i64, P, P, P, P, P, P, PS, P]),
+        "ctr_unique_ids": (i32, [P, i32, i64, P, i64, i32, P, i64, i64, P, P, P, P, P, P, P, PS, P]),
         "ctr_gather_rows": (i32, [P, i32, i64, i32, P, P, i64, P, P]),
         "ctr_embbag_fwd": (i32, [P, i32, i64, i32, P, i32, P, i32, i64, P, i64, P, i64, i64, P]),
-        "ctr_embbag_bwd": (i32, [P, i64, i64, P, i64, i32, i32, i64, P, P, P, P, P, PS, P]),
+        "ctr_embbag_bwd": (i32, [P, i64, i64, P, i64, i32, i32, i64, P, P, P, P, P, P, PS, P]),
+        "ctr_embbag_bwd_sgd": (i32, [P, i64, i64, P, i64, i32, i64, P, P, P, i32, i64, i32, P,
+                                     f32, P, P, PS, P]),
         "ctr_sparse_sgd": (i32, [P, i32, i64, i32, P, P, i64, P, f32, P]),
         "ctr_dot_interaction_fwd": (i32, [P, i64, i32, i32, i32, P, i64, P]),
         "ctr_dot_interaction_bwd": (i32, [P, P, i64, i64, i32, i32, i32, P, P]),
@@ -86,6 +89,29 @@ def _check(fn: str, status: int) -> None:
         raise CtrError(fn, status, load().ctr_last_error().decode())
 
 
+class Call:
+    """A libctr call whose arguments were marshalled once; calling it only reads the current
+    stream (so it also works under stream capture) and checks the status."""
+    __slots__ = ("name", "fn", "args", "result")
+
+    def __init__(self, name: str, args: tuple, result=None):
+        self.name = name
+        self.fn = getattr(load(), name)
+        self.args = args
+        self.result = result
+
+    def __call__(self, stream=None):
+        st = self.fn(*self.args, _stream(stream))
+        if st != CTR_OK:
+            _check(self.name, st)
+        return self.result
+
+
+def _run(name: str, args: tuple, stream, prepare: bool, result=None):
+    call = Call(name, args, result)
+    return call if prepare else call(stream)
+
+
 def _dtype_code(t: torch.Tensor) -> int:
     if t.dtype == torch.float32:
         return CTR_F32
@@ -110,7 +136,7 @@ def unique_workspace_bytes(n: int) -> int:
     """Workspace of ctr_unique_ids for n occurrences (the library's two-call query)."""
     wsb = ctypes.c_size_t(0)
     _check("ctr_unique_ids", load().ctr_unique_ids(None, CTR_I64, n, None, 0, 0, None, 0, 0,
-                                                   None, None, None, None, None, None,
+                                                   None, None, None, None, None, None, None,
                                                    ctypes.byref(wsb), None))
     return wsb.value
 
@@ -119,7 +145,8 @@ def embbag_bwd_workspace_bytes(nnz: int, dim: int) -> int:
     """Workspace of ctr_embbag_bwd (the library's two-call query)."""
     wsb = ctypes.c_size_t(0)
     _check("ctr_embbag_bwd", load().ctr_embbag_bwd(None, 0, 0, None, 1, 1, dim, nnz, None, None,
-                                                   None, None, None, ctypes.byref(wsb), None))
+                                                   None, None, None, None, ctypes.byref(wsb),
+                                                   None))
     return wsb.value
 
 
@@ -132,13 +159,14 @@ def ctr_unique_ids(ids: torch.Tensor, *, offsets: Optional[torch.Tensor] = None,
                    num_tables: int = 0, row_base: Optional[torch.Tensor] = None,
                    total_rows: int = 0, key_modulus: int = 0, want_perm: bool = True,
                    want_seg: bool = True, workspace: Optional[torch.Tensor] = None,
-                   out: Optional[tuple] = None, stream=None
+                   out: Optional[tuple] = None, sorted_src: Optional[torch.Tensor] = None,
+                   stream=None, prepare: bool = False
                    ) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor, Optional[torch.Tensor],
                               Optional[torch.Tensor]]:
     """Returns (uniq int64[n], inverse int32[n], num_unique int32[1], perm, seg_offsets);
     only the first num_unique entries of uniq (and num_unique+1 of seg_offsets) are set.
-    ``out`` may supply those five tensors (perm / seg_offsets may be None)."""
-    lib = load()
+    ``out`` may supply those five tensors (perm / seg_offsets may be None); ``sorted_src``
+    (int32 [n, 2]) receives the (distinct-row index, bag) pair of every sorted position."""
     n = ids.numel()
     dev = ids.device
     if out is not None:
@@ -155,88 +183,102 @@ def ctr_unique_ids(ids: torch.Tensor, *, offsets: Optional[torch.Tensor] = None,
         workspace = _workspace(unique_workspace_bytes(n), dev)
     ws = workspace
     wsb = ctypes.c_size_t(ws.numel())
-    _check("ctr_unique_ids", lib.ctr_unique_ids(*args, _ptr(uniq), _ptr(inv), _ptr(nu),
-                                                _ptr(perm), _ptr(seg), _ptr(ws),
-                                                ctypes.byref(wsb), _stream(stream)))
-    return uniq[:n], inv[:n], nu, (perm[:n] if perm is not None else None), seg
+    full = args + (_ptr(uniq), _ptr(inv), _ptr(nu), _ptr(perm), _ptr(seg), _ptr(sorted_src),
+                   _ptr(ws), ctypes.byref(wsb))
+    res = (uniq[:n], inv[:n], nu, (perm[:n] if perm is not None else None), seg)
+    return _run("ctr_unique_ids", full, stream, prepare, res)
 
 
 def ctr_gather_rows(table: torch.Tensor, rows: torch.Tensor, num_rows: torch.Tensor,
-                    capacity: int, out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
-    lib = load()
+                    capacity: int, out: Optional[torch.Tensor] = None, stream=None,
+                    prepare: bool = False):
     total_rows, dim = table.shape
     if out is None:
         out = torch.empty((max(capacity, 1), dim), dtype=torch.float32, device=table.device)
-    _check("ctr_gather_rows", lib.ctr_gather_rows(_ptr(table), _dtype_code(table), total_rows, dim,
-                                                  _ptr(rows), _ptr(num_rows), capacity, _ptr(out),
-                                                  _stream(stream)))
-    return out
+    args = (_ptr(table), _dtype_code(table), total_rows, dim, _ptr(rows), _ptr(num_rows),
+            capacity, _ptr(out))
+    return _run("ctr_gather_rows", args, stream, prepare, out)
 
 
 def ctr_embbag_fwd(table: torch.Tensor, indices: torch.Tensor, offsets: torch.Tensor,
                    batch: int, num_tables: int, out: torch.Tensor, out_stride_b: int,
                    out_stride_t: int, row_base: Optional[torch.Tensor] = None,
-                   stream=None) -> torch.Tensor:
-    lib = load()
+                   stream=None, prepare: bool = False):
     total_rows, dim = table.shape
-    _check("ctr_embbag_fwd", lib.ctr_embbag_fwd(
-        _ptr(table), _dtype_code(table), total_rows, dim, _ptr(row_base), num_tables,
-        _ptr(indices), _index_code(indices), indices.numel(), _ptr(offsets), batch, _ptr(out),
-        out_stride_b, out_stride_t, _stream(stream)))
-    return out
+    args = (_ptr(table), _dtype_code(table), total_rows, dim, _ptr(row_base), num_tables,
+            _ptr(indices), _index_code(indices), indices.numel(), _ptr(offsets), batch, _ptr(out),
+            out_stride_b, out_stride_t)
+    return _run("ctr_embbag_fwd", args, stream, prepare, out)
 
 
 def ctr_embbag_bwd(grad: torch.Tensor, grad_stride_b: int, grad_stride_t: int,
                    offsets: torch.Tensor, batch: int, num_tables: int, dim: int,
-                   perm: torch.Tensor, inverse: torch.Tensor, num_unique: torch.Tensor,
-                   row_grads: Optional[torch.Tensor] = None,
-                   workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
-    lib = load()
-    nnz = perm.numel()
+                   perm: Optional[torch.Tensor], inverse: Optional[torch.Tensor],
+                   num_unique: torch.Tensor, row_grads: Optional[torch.Tensor] = None,
+                   workspace: Optional[torch.Tensor] = None,
+                   sorted_src: Optional[torch.Tensor] = None, nnz: Optional[int] = None,
+                   stream=None, prepare: bool = False):
+    """Per-row gradient sums; the grouping comes from ``sorted_src`` or from (perm, inverse)."""
+    if nnz is None:
+        nnz = sorted_src.shape[0] if sorted_src is not None else perm.numel()
     dev = grad.device
     if row_grads is None:
         row_grads = torch.empty((max(nnz, 1), dim), dtype=torch.float32, device=dev)
     args = (_ptr(grad), grad_stride_b, grad_stride_t, _ptr(offsets), batch, num_tables, dim, nnz,
-            _ptr(perm), _ptr(inverse), _ptr(num_unique), _ptr(row_grads))
+            _ptr(perm), _ptr(inverse), _ptr(sorted_src), _ptr(num_unique), _ptr(row_grads))
     if workspace is None:
         workspace = _workspace(embbag_bwd_workspace_bytes(nnz, dim), dev)
     ws = workspace
     wsb = ctypes.c_size_t(ws.numel())
-    _check("ctr_embbag_bwd", lib.ctr_embbag_bwd(*args, _ptr(ws), ctypes.byref(wsb), _stream(stream)))
-    return row_grads
+    return _run("ctr_embbag_bwd", args + (_ptr(ws), ctypes.byref(wsb)), stream, prepare,
+                row_grads)
+
+
+def ctr_embbag_bwd_sgd(grad: torch.Tensor, grad_stride_b: int, grad_stride_t: int,
+                       offsets: torch.Tensor, batch: int, num_tables: int, nnz: int,
+                       sorted_src: torch.Tensor, num_unique: torch.Tensor, table: torch.Tensor,
+                       uniq: torch.Tensor, lr: float, row_grads: Optional[torch.Tensor] = None,
+                       workspace: Optional[torch.Tensor] = None, stream=None,
+                       prepare: bool = False):
+    """Per-row gradient sums applied straight to the table as the sparse SGD update."""
+    total_rows, dim = table.shape
+    if workspace is None:
+        workspace = _workspace(embbag_bwd_workspace_bytes(nnz, dim), grad.device)
+    wsb = ctypes.c_size_t(workspace.numel())
+    args = (_ptr(grad), grad_stride_b, grad_stride_t, _ptr(offsets), batch, num_tables, nnz,
+            _ptr(sorted_src), _ptr(num_unique), _ptr(table), _dtype_code(table), total_rows, dim,
+            _ptr(uniq), ctypes.c_float(lr), _ptr(row_grads), _ptr(workspace), ctypes.byref(wsb))
+    return _run("ctr_embbag_bwd_sgd", args, stream, prepare, row_grads)
 
 
 def ctr_sparse_sgd(table: torch.Tensor, uniq: torch.Tensor, num_unique: torch.Tensor,
-                   capacity: int, row_grads: torch.Tensor, lr: float, stream=None) -> None:
-    lib = load()
+                   capacity: int, row_grads: torch.Tensor, lr: float, stream=None,
+                   prepare: bool = False):
     total_rows, dim = table.shape
-    _check("ctr_sparse_sgd", lib.ctr_sparse_sgd(_ptr(table), _dtype_code(table), total_rows, dim,
-                                                _ptr(uniq), _ptr(num_unique), capacity,
-                                                _ptr(row_grads), ctypes.c_float(lr),
-                                                _stream(stream)))
+    args = (_ptr(table), _dtype_code(table), total_rows, dim, _ptr(uniq), _ptr(num_unique),
+            capacity, _ptr(row_grads), ctypes.c_float(lr))
+    return _run("ctr_sparse_sgd", args, stream, prepare)
 
 
 def ctr_dot_interaction_fwd(Z: torch.Tensor, compute: int = CTR_F32,
-                            R: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
-    lib = load()
+                            R: Optional[torch.Tensor] = None, stream=None,
+                            prepare: bool = False):
     B, F, d = Z.shape
     P = F * (F - 1) // 2
     if R is None:
         R = torch.empty((B, d + P), dtype=torch.float32, device=Z.device)
-    _check("ctr_dot_interaction_fwd", lib.ctr_dot_interaction_fwd(
-        _ptr(Z), B, F, d, compute, _ptr(R), R.stride(0), _stream(stream)))
-    return R
+    args = (_ptr(Z), B, F, d, compute, _ptr(R), R.stride(0))
+    return _run("ctr_dot_interaction_fwd", args, stream, prepare, R)
 
 
 def ctr_dot_interaction_bwd(Z: torch.Tensor, dR: torch.Tensor, compute: int = CTR_F32,
-                            dZ: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
-    lib = load()
+                            dZ: Optional[torch.Tensor] = None, stream=None,
+                            prepare: bool = False):
     B, F, d = Z.shape
     if dZ is None:
         dZ = torch.empty_like(Z)
-    _check("ctr_dot_interaction_bwd", lib.ctr_dot_interaction_bwd(
-        _ptr(Z), _ptr(dR), dR.stride(0), B, F, d, compute, _ptr(dZ), _stream(stream)))
-    return dZ
+    args = (_ptr(Z), _ptr(dR), dR.stride(0), B, F, d, compute, _ptr(dZ))
+    return _run("ctr_dot_interaction_bwd", args, stream, prepare, dZ)
 
 
 def ctr_init_table_hash(table: torch.Tensor, rows: Sequence[int], seed: int, stream=None) -> None:

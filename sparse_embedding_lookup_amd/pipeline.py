@@ -31,8 +31,14 @@ def _dev(a: np.ndarray, device) -> torch.Tensor:
 class FrontEnd:
     """Device state for one workload: the tables, the batch and every buffer of the path."""
 
-    def __init__(self, w: Workload, device="cuda", table: Optional[torch.Tensor] = None):
+    def __init__(self, w: Workload, device="cuda", table: Optional[torch.Tensor] = None,
+                 fused: bool = True, keep_grads: bool = False):
+        """fused: the backward applies the sparse SGD as each row gradient completes
+        (ctr_embbag_bwd_sgd); otherwise ctr_embbag_bwd then ctr_sparse_sgd.  keep_grads: also
+        keep the per-row gradients in self.row_grads (always kept when not fused)."""
         self.w = w
+        self.fused = fused
+        self.keep_grads = keep_grads or not fused
         self.device = torch.device(device)
         self.bf16 = w.dtype == "bf16"
         self.compute = ctr.CTR_BF16 if w.compute == "bf16" else ctr.CTR_F32
@@ -58,8 +64,8 @@ class FrontEnd:
             self.E = torch.empty((max(n, 1), d), dtype=torch.float32, device=self.device)
             self.out = torch.empty((max(n, 1), d), dtype=torch.float32, device=self.device)
             self.dout = _dev(w.grad_out.reshape(n, d), self.device)
-        self.row_grads = torch.empty((max(self.nnz, 1), d), dtype=torch.float32,
-                                     device=self.device)
+        self.row_grads = (torch.empty((max(self.nnz, 1), d), dtype=torch.float32,
+                                      device=self.device) if self.keep_grads else None)
         n = self.nnz
         dv = self.device
         self.ws_unique = torch.empty(max(ctr.unique_workspace_bytes(n), 256), dtype=torch.uint8,
@@ -71,67 +77,95 @@ class FrontEnd:
         self.num_unique = torch.zeros(1, dtype=torch.int32, device=dv)
         self.perm = torch.empty(max(n, 1), dtype=torch.int32, device=dv)
         self.seg = torch.empty(n + 1, dtype=torch.int32, device=dv)
+        self.sorted_src = torch.empty((max(n, 1), 2), dtype=torch.int32, device=dv)
         self._unique_out = (self.uniq, self.inverse, self.num_unique, self.perm, self.seg)
         self.side = None
 
+        self._prepare()
+
     # ------------------------------------------------------------------ steps of the path
-    def unique(self):
-        w = self.w
-        if w.interaction:
-            ctr.ctr_unique_ids(self.indices, offsets=self.offsets, batch=w.batch,
-                               num_tables=w.num_tables, row_base=self.row_base,
-                               total_rows=w.total_rows, workspace=self.ws_unique,
-                               out=self._unique_out)
-        else:
-            ctr.ctr_unique_ids(self.indices, key_modulus=w.key_modulus, workspace=self.ws_unique,
-                               out=self._unique_out)
-
-    def _embbag_fwd(self):
-        w = self.w
-        if w.interaction:
-            F, d = w.F, w.dim
-            ctr.ctr_embbag_fwd(self.table, self.indices, self.offsets, w.batch, w.num_tables,
-                               self.Z[:, 1:, :], F * d, d, row_base=self.row_base)
-        else:
-            ctr.ctr_embbag_fwd(self.E, self.inverse, self.offsets, self.nnz, 1, self.out,
-                               w.dim, 0)
-
-    def _gather_rows(self):
-        ctr.ctr_gather_rows(self.table, self.uniq, self.num_unique, self.nnz, out=self.E)
-
-    def _interaction_fwd(self):
-        ctr.ctr_dot_interaction_fwd(self.Z, self.compute, self.R)
-
-    def _interaction_bwd(self):
-        ctr.ctr_dot_interaction_bwd(self.Z, self.dR, self.compute, self.dZ)
-
-    def _embbag_bwd(self):
+    def _prepare(self):
+        """Marshal every call of the step once (buffers never move)."""
         w = self.w
         d = w.dim
-        perm = self.perm[:self.nnz]
+        P = dict(prepare=True)
         if w.interaction:
             F = w.F
-            ctr.ctr_embbag_bwd(self.dZ[:, 1:, :], F * d, d, self.offsets, w.batch,
-                               w.num_tables, d, perm, self.inverse, self.num_unique,
-                               self.row_grads, workspace=self.ws_bwd)
+            self._c_unique = ctr.ctr_unique_ids(
+                self.indices, offsets=self.offsets, batch=w.batch, num_tables=w.num_tables,
+                row_base=self.row_base, total_rows=w.total_rows, workspace=self.ws_unique,
+                out=self._unique_out, sorted_src=self.sorted_src, **P)
+            self._c_embbag_fwd = ctr.ctr_embbag_fwd(
+                self.table, self.indices, self.offsets, w.batch, w.num_tables, self.Z[:, 1:, :],
+                F * d, d, row_base=self.row_base, **P)
+            self._c_interaction_fwd = ctr.ctr_dot_interaction_fwd(self.Z, self.compute, self.R, **P)
+            self._c_interaction_bwd = ctr.ctr_dot_interaction_bwd(self.Z, self.dR, self.compute,
+                                                                  self.dZ, **P)
+            if not self.fused:
+                self._c_embbag_bwd = ctr.ctr_embbag_bwd(
+                    self.dZ[:, 1:, :], F * d, d, self.offsets, w.batch, w.num_tables, d, None,
+                    None, self.num_unique, self.row_grads, workspace=self.ws_bwd,
+                    sorted_src=self.sorted_src, nnz=self.nnz, **P)
         else:
-            ctr.ctr_embbag_bwd(self.dout, d, 0, self.offsets, self.nnz, 1, d, perm,
-                               self.inverse, self.num_unique, self.row_grads,
-                               workspace=self.ws_bwd)
+            self._c_unique = ctr.ctr_unique_ids(
+                self.indices, key_modulus=w.key_modulus, workspace=self.ws_unique,
+                out=self._unique_out, sorted_src=self.sorted_src, **P)
+            self._c_gather_rows = ctr.ctr_gather_rows(self.table, self.uniq, self.num_unique,
+                                                      self.nnz, out=self.E, **P)
+            self._c_embbag_fwd = ctr.ctr_embbag_fwd(self.E, self.inverse, self.offsets, self.nnz,
+                                                    1, self.out, d, 0, **P)
+            if not self.fused:
+                self._c_embbag_bwd = ctr.ctr_embbag_bwd(
+                    self.dout, d, 0, self.offsets, self.nnz, 1, d, None, None,
+                    self.num_unique, self.row_grads, workspace=self.ws_bwd,
+                    sorted_src=self.sorted_src, nnz=self.nnz, **P)
+        if self.fused:
+            if w.interaction:
+                F = w.F
+                grad, sb, st, B, T = self.dZ[:, 1:, :], F * d, d, w.batch, w.num_tables
+            else:
+                grad, sb, st, B, T = self.dout, d, 0, self.nnz, 1
+            self._c_embbag_bwd_sgd = ctr.ctr_embbag_bwd_sgd(
+                grad, sb, st, self.offsets, B, T, self.nnz, self.sorted_src, self.num_unique,
+                self.table, self.uniq, w.lr, row_grads=self.row_grads, workspace=self.ws_bwd,
+                **P)
+        else:
+            self._c_sparse_sgd = ctr.ctr_sparse_sgd(self.table, self.uniq, self.num_unique,
+                                                    self.nnz, self.row_grads, w.lr, **P)
+
+    def unique(self):
+        self._c_unique()
+
+    def _embbag_fwd(self):
+        self._c_embbag_fwd()
+
+    def _gather_rows(self):
+        self._c_gather_rows()
+
+    def _interaction_fwd(self):
+        self._c_interaction_fwd()
+
+    def _interaction_bwd(self):
+        self._c_interaction_bwd()
+
+    def _embbag_bwd(self):
+        self._c_embbag_bwd()
 
     def _sparse_sgd(self):
-        ctr.ctr_sparse_sgd(self.table, self.uniq, self.num_unique, self.nnz, self.row_grads,
-                           self.w.lr)
+        self._c_sparse_sgd()
+
+    def _embbag_bwd_sgd(self):
+        self._c_embbag_bwd_sgd()
 
     def stages(self):
         """The step's calls in dependency order, as (name, fn)."""
+        tail = ([("embbag_bwd_sgd", self._embbag_bwd_sgd)] if self.fused else
+                [("embbag_bwd", self._embbag_bwd), ("sparse_sgd", self._sparse_sgd)])
         if self.w.interaction:
             return [("embbag_fwd", self._embbag_fwd), ("interaction_fwd", self._interaction_fwd),
-                    ("interaction_bwd", self._interaction_bwd), ("unique", self.unique),
-                    ("embbag_bwd", self._embbag_bwd), ("sparse_sgd", self._sparse_sgd)]
+                    ("interaction_bwd", self._interaction_bwd), ("unique", self.unique)] + tail
         return [("unique", self.unique), ("gather_rows", self._gather_rows),
-                ("embbag_fwd", self._embbag_fwd), ("embbag_bwd", self._embbag_bwd),
-                ("sparse_sgd", self._sparse_sgd)]
+                ("embbag_fwd", self._embbag_fwd)] + tail
 
     def forward(self):
         if self.w.interaction:
@@ -146,28 +180,72 @@ class FrontEnd:
         if self.w.interaction:
             self._interaction_bwd()
             self.unique()
-        self._embbag_bwd()
-        self._sparse_sgd()
+        if self.fused:
+            self._embbag_bwd_sgd()
+        else:
+            self._embbag_bwd()
+            self._sparse_sgd()
 
-    def step(self, mark=None):
-        """One training step.  With tables and a dense vector, the batch's unique runs on a
-        second stream (default priority) beside the forward and the interaction gradient,
-        which do not need it.  ``mark(name, fn)`` may wrap a stage (e.g. with events on the
-        stream it runs on); by default it just calls it."""
-        run = mark if mark is not None else (lambda name, fn: fn())
-        if not self.w.interaction:
-            for name, fn in self.stages():
-                run(name, fn)
+    def run(self, names, mark=None):
+        """Run the named stages in step order.  With tables and a dense vector the batch's
+        unique runs on a second stream (default priority), forked when the segment starts
+        and joined before its first consumer (or at the end of the segment), so it overlaps
+        the forward and the interaction gradient.  ``mark(name, fn)`` may wrap a stage."""
+        go = mark if mark is not None else (lambda name, fn: fn())
+        fns = dict(self.stages())
+        order = [n for n, _ in self.stages() if n in names]
+        if not self.w.interaction or "unique" not in order:
+            for n in order:
+                go(n, fns[n])
             return
         main = torch.cuda.current_stream(self.device)
         if self.side is None:
             self.side = torch.cuda.Stream(device=self.device)
         self.side.wait_stream(main)
         with torch.cuda.stream(self.side):
-            run("unique", self.unique)
-        run("embbag_fwd", self._embbag_fwd)
-        run("interaction_fwd", self._interaction_fwd)
-        run("interaction_bwd", self._interaction_bwd)
-        main.wait_stream(self.side)
-        run("embbag_bwd", self._embbag_bwd)
-        run("sparse_sgd", self._sparse_sgd)
+            go("unique", self.unique)
+        pending = True
+        for n in order:
+            if n == "unique":
+                continue
+            if pending and n in ("embbag_bwd", "sparse_sgd", "embbag_bwd_sgd"):
+                main.wait_stream(self.side)
+                pending = False
+            go(n, fns[n])
+        if pending:
+            main.wait_stream(self.side)
+
+    def step(self, mark=None):
+        """One training step (all stages)."""
+        self.run([n for n, _ in self.stages()], mark)
+
+    def split(self, at: str):
+        """Stage names before `at`, and after it, such that the unique lands in a segment
+        that precedes its consumers.  Used to time one kernel between captured segments."""
+        names = [n for n, _ in self.stages()]
+        main = [n for n in names if n != "unique"] if self.w.interaction else names
+        if at == "unique":
+            i = names.index("unique")
+            return names[:i], names[i + 1:]
+        i = main.index(at)
+        pre, post = main[:i], main[i + 1:]
+        if self.w.interaction:            # the unique goes with the earliest segment
+            if pre:
+                pre = pre + ["unique"]
+            else:
+                post = post + ["unique"]
+        return pre, post
+
+    def capture(self, names=None, steps: int = 1):
+        """Record `steps` repetitions of the named stages (default: the whole step) into one
+        HIP graph; replay with .replay().  The step allocates nothing, so the graph holds
+        only the library's kernel launches and the stream fork/join."""
+        if names is None:
+            names = [n for n, _ in self.stages()]
+        if self.w.interaction and self.side is None:
+            self.side = torch.cuda.Stream(device=self.device)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(steps):
+                self.run(names)
+        return g

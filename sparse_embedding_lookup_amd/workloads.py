@@ -207,6 +207,26 @@ def large(seed: int = 0, batch: int = 32768, tables: int = 64, rows: int = 4_000
                     _offsets_from_lengths(lengths), dense, grad, 0.01, "bf16")
 
 
+def slice_batch(w: Workload, b: int) -> Workload:
+    """The first `b` samples of every table (a bounded sample of the same batch)."""
+    b = min(int(b), w.batch)
+    if not w.interaction:                        # one occurrence per (sample, slot)
+        n = b * w.slots
+        return dataclasses.replace(w, batch=b, indices=w.indices[:n],
+                                   offsets=np.arange(n + 1, dtype=np.int64),
+                                   grad_out=w.grad_out[:b])
+    T, B = w.num_tables, w.batch
+    parts, lens = [], []
+    for t in range(T):
+        lo, hi = int(w.offsets[t * B]), int(w.offsets[t * B + b])
+        parts.append(w.indices[lo:hi])
+        lens.append(np.diff(w.offsets[t * B:t * B + b + 1]))
+    off = np.zeros(T * b + 1, dtype=np.int64)
+    np.cumsum(np.concatenate(lens), out=off[1:])
+    return dataclasses.replace(w, batch=b, indices=np.concatenate(parts), offsets=off,
+                               dense=w.dense[:b], grad_out=w.grad_out[:b])
+
+
 BUILDERS = {"tiny": tiny, "small": small, "criteo": criteo, "tensornet": tensornet,
             "large": large}
 

@@ -59,21 +59,21 @@ def test_unique_workspace_query_and_bad_args():
     lib = _lib()
     wsb = ctypes.c_size_t(0)
     assert lib.ctr_unique_ids(None, 1, 1000, None, 0, 0, None, 0, 0, None, None, None, None,
-                              None, None, ctypes.byref(wsb), None) == ctr.CTR_OK
+                              None, None, None, ctypes.byref(wsb), None) == ctr.CTR_OK
     assert wsb.value >= 1000 * 24
     bad = ctypes.c_size_t(10)
     st = lib.ctr_unique_ids(FAKE, 1, 1000, None, 0, 0, None, 0, 0, FAKE, FAKE, FAKE, None, None,
-                            FAKE, ctypes.byref(bad), None)
+                            None, FAKE, ctypes.byref(bad), None)
     assert st == ctr.CTR_ERR_WORKSPACE_TOO_SMALL
     assert lib.ctr_unique_ids(FAKE, 1, -1, None, 0, 0, None, 0, 0, None, None, None, None, None,
-                              None, ctypes.byref(wsb), None) == ctr.CTR_ERR_INVALID_ARGUMENT
-    assert lib.ctr_unique_ids(FAKE, 1, 2 ** 31, None, 0, 0, None, 0, 0, None, None, None, None,
                               None, None, ctypes.byref(wsb), None) == ctr.CTR_ERR_INVALID_ARGUMENT
+    assert lib.ctr_unique_ids(FAKE, 1, 2 ** 31, None, 0, 0, None, 0, 0, None, None, None, None,
+                              None, None, None, ctypes.byref(wsb), None) == ctr.CTR_ERR_INVALID_ARGUMENT
     assert lib.ctr_unique_ids(FAKE, 7, 10, None, 0, 0, None, 0, 0, None, None, None, None, None,
-                              None, ctypes.byref(wsb), None) == ctr.CTR_ERR_INVALID_ARGUMENT
+                              None, None, ctypes.byref(wsb), None) == ctr.CTR_ERR_INVALID_ARGUMENT
     # row_base without offsets
     assert lib.ctr_unique_ids(FAKE, 1, 10, None, 4, 2, FAKE, 100, 0, None, None, None, None, None,
-                              None, ctypes.byref(wsb), None) == ctr.CTR_ERR_INVALID_ARGUMENT
+                              None, None, ctypes.byref(wsb), None) == ctr.CTR_ERR_INVALID_ARGUMENT
     assert b"offsets" in lib.ctr_last_error()
 
 
@@ -106,16 +106,19 @@ def test_embbag_bwd_workspace_and_bad_args():
     lib = _lib()
     wsb = ctypes.c_size_t(0)
     assert lib.ctr_embbag_bwd(None, 64, 0, None, 10, 1, 64, 1000, None, None, None, None, None,
-                              ctypes.byref(wsb), None) == ctr.CTR_OK
+                              None, ctypes.byref(wsb), None) == ctr.CTR_OK
     assert wsb.value >= 1000 * 12
     assert lib.ctr_embbag_bwd(None, 64, 0, None, 10, 1, 6, 1000, None, None, None, None, None,
-                              ctypes.byref(wsb), None) == ctr.CTR_ERR_UNSUPPORTED
+                              None, ctypes.byref(wsb), None) == ctr.CTR_ERR_UNSUPPORTED
     small = ctypes.c_size_t(16)
-    assert lib.ctr_embbag_bwd(FAKE, 64, 0, FAKE, 10, 1, 64, 1000, FAKE, FAKE, FAKE, FAKE, FAKE,
-                              ctypes.byref(small), None) == ctr.CTR_ERR_WORKSPACE_TOO_SMALL
+    assert lib.ctr_embbag_bwd(FAKE, 64, 0, FAKE, 10, 1, 64, 1000, FAKE, FAKE, None, FAKE, FAKE,
+                              FAKE, ctypes.byref(small), None) == ctr.CTR_ERR_WORKSPACE_TOO_SMALL
     big = ctypes.c_size_t(wsb.value)
-    assert lib.ctr_embbag_bwd(MISALIGNED, 64, 0, FAKE, 10, 1, 64, 1000, FAKE, FAKE, FAKE, FAKE,
-                              FAKE, ctypes.byref(big), None) == ctr.CTR_ERR_UNSUPPORTED
+    assert lib.ctr_embbag_bwd(MISALIGNED, 64, 0, FAKE, 10, 1, 64, 1000, FAKE, FAKE, None, FAKE,
+                              FAKE, FAKE, ctypes.byref(big), None) == ctr.CTR_ERR_UNSUPPORTED
+    # neither sorted_src nor (perm, inverse)
+    assert lib.ctr_embbag_bwd(FAKE, 64, 0, FAKE, 10, 1, 64, 1000, None, FAKE, None, FAKE, FAKE,
+                              FAKE, ctypes.byref(big), None) == ctr.CTR_ERR_INVALID_ARGUMENT
 
 
 def test_interaction_bad_args():

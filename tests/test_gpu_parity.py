@@ -116,6 +116,34 @@ def test_unique_matches_oracle(name):
     np.testing.assert_array_equal(seg[:U + 1], os_)
 
 
+@pytest.mark.parametrize("name", ["tiny_tables", "small_tables", "tensornet_mod", "all_equal",
+                                  "raw_signed"])
+def test_unique_sorted_src(name):
+    """(u, bag) per sorted position: u = inverse[perm[p]], bag = bag holding perm[p] (or the
+    occurrence itself without bags)."""
+    ids, kw = UNIQUE_CASES[name]
+    say("unique sorted_src", name)
+    n = ids.size
+    src = torch.empty((n, 2), dtype=torch.int32, device=DEV)
+    if "offsets" in kw:
+        rb = np.zeros(len(kw["rows"]) + 1, dtype=np.int64)
+        rb[1:] = np.cumsum(kw["rows"])
+        keys = orc.form_keys(ids, kw["offsets"], kw["T"], kw["batch"], rb)
+        ctr.ctr_unique_ids(dev(ids), offsets=dev(kw["offsets"]), batch=kw["batch"],
+                           num_tables=kw["T"], row_base=dev(rb), total_rows=int(rb[-1]),
+                           sorted_src=src)
+        bag_of = np.searchsorted(kw["offsets"], np.arange(n), side="right") - 1
+    else:
+        m = kw.get("modulus", 0)
+        keys = orc.form_keys(ids.astype(np.int64), np.array([0, n]), 1, 1, None, m)
+        ctr.ctr_unique_ids(dev(ids), key_modulus=m, sorted_src=src)
+        bag_of = np.arange(n)
+    ou, oi, op, os_ = orc.unique(keys)
+    got = host(src)
+    np.testing.assert_array_equal(got[:, 0], oi[op])
+    np.testing.assert_array_equal(got[:, 1], bag_of[op])
+
+
 def test_unique_empty():
     res = ctr.ctr_unique_ids(torch.zeros(0, dtype=torch.int64, device=DEV), key_modulus=10)
     nu, seg = host(res[2]), host(res[4])
@@ -300,6 +328,12 @@ def test_embbag_bwd_matches_oracle(name):
     got = host(rg)[:U]
     want, mag = orc.embbag_bwd(dZ[:, 1:, :].astype(np.float64), off, B, T, inv, U)
     assert_close(got, want, mag, RTOL_F32, "embbag_bwd " + name)
+    # the same through (u, bag) pairs per sorted position, as the unique step emits them
+    bag_of = np.searchsorted(off, np.arange(len(ids)), side="right") - 1
+    pairs = np.stack([inv[perm], bag_of[perm]], axis=1).astype(np.int32)
+    rg2 = ctr.ctr_embbag_bwd(g_dev[:, 1:, :], (T + 1) * dim, dim, dev(off), B, T, dim, None, None,
+                             dev(np.array([U], np.int32)), sorted_src=dev(pairs), nnz=len(ids))
+    np.testing.assert_array_equal(host(rg2)[:U], got)
 
 
 # ----------------------------------------------------------------------------- SGD
@@ -365,7 +399,7 @@ def test_end_to_end_dlrm_step(name):
     w = {"tiny": workloads.tiny, "small_b256": lambda: workloads.small(batch=256),
          "criteo_b128": lambda: workloads.criteo(batch=128)}[name]()
     say("end_to_end", name, w.nnz)
-    fe = FrontEnd(w, DEV)
+    fe = FrontEnd(w, DEV, keep_grads=True)
     fe.step()
     o = _oracle_dlrm_step(w)
     rt = RTOL_BF16 if w.compute == "bf16" else RTOL_F32
@@ -387,7 +421,7 @@ def test_end_to_end_dlrm_step(name):
 def test_end_to_end_tensornet_step_reduced():
     w = workloads.tensornet(batch=2048, slots=100)
     say("end_to_end tensornet", w.nnz)
-    fe = FrontEnd(w, DEV)
+    fe = FrontEnd(w, DEV, keep_grads=True)
     fe.step()
     tab = orc.Table(w.rows, w.dim, w.dtype, w.table_seed)
     keys = orc.form_keys(w.indices, w.offsets, 1, w.nnz, np.array([0, w.rows[0]]), w.key_modulus)
@@ -411,7 +445,7 @@ def test_step_is_deterministic():
     w = workloads.small(batch=256)
     outs = []
     for _ in range(2):
-        fe = FrontEnd(w, DEV)
+        fe = FrontEnd(w, DEV, keep_grads=True)
         fe.step()
         U = int(host(fe.num_unique)[0])
         outs.append((host(fe.R).copy(), host(fe.dZ).copy(), host(fe.row_grads)[:U].copy(),
@@ -432,3 +466,54 @@ def test_validate_csr_counts_violations():
     ctr.ctr_validate_csr(dev(np.array([0, 1, 2], np.int64)), dev(np.array([0, 2, 1, 3], np.int64)),
                          3, 1, bad, total_rows=5)
     assert int(host(bad)[0]) == 1                          # offsets decrease once
+
+
+@pytest.mark.parametrize("name", ["small_b256", "tensornet_b256"])
+def test_graph_replay_matches_eager(name):
+    """A captured step replayed several times, with unrelated eager work and synchronizations
+    in between, gives bit-identical results to the same steps run eagerly."""
+    w = (workloads.small(batch=256) if name == "small_b256"
+         else workloads.tensornet(batch=256, slots=100, table_rows=200_000))
+    say("graph replay", name)
+    fa = FrontEnd(w, DEV, keep_grads=True)
+    fb = FrontEnd(w, DEV, keep_grads=True)
+    fa.step()
+    fb.step()
+    torch.cuda.synchronize()
+    g = fb.capture()
+    junk = torch.randn(1 << 20, device=DEV)
+    for r in range(3):
+        fa.step()
+        g.replay()
+        junk.mul_(1.0001).add_(1.0)            # unrelated eager work between replays
+        torch.cuda.synchronize()
+        U = int(host(fa.num_unique)[0])
+        assert U == int(host(fb.num_unique)[0])
+        np.testing.assert_array_equal(host(fa.uniq)[:U], host(fb.uniq)[:U])
+        np.testing.assert_array_equal(host(fa.row_grads)[:U], host(fb.row_grads)[:U])
+        if w.interaction:
+            np.testing.assert_array_equal(host(fa.R), host(fb.R))
+            np.testing.assert_array_equal(host(fa.dZ), host(fb.dZ))
+        else:
+            np.testing.assert_array_equal(host(fa.out), host(fb.out))
+        rows = fa.uniq[:U]
+        np.testing.assert_array_equal(host(fa.table[rows].float()), host(fb.table[rows].float()))
+
+
+@pytest.mark.parametrize("name", ["small_b256", "criteo_b128", "tensornet_b512"])
+def test_fused_backward_sgd_matches_two_calls(name):
+    """ctr_embbag_bwd_sgd leaves the table bit-identical to ctr_embbag_bwd + ctr_sparse_sgd
+    and produces the same per-row gradients."""
+    w = {"small_b256": lambda: workloads.small(batch=256),
+         "criteo_b128": lambda: workloads.criteo(batch=128),
+         "tensornet_b512": lambda: workloads.tensornet(batch=512, slots=100,
+                                                       table_rows=500_000)}[name]()
+    say("fused bwd+sgd", name)
+    fa = FrontEnd(w, DEV, fused=True, keep_grads=True)
+    fb = FrontEnd(w, DEV, fused=False)
+    for _ in range(2):
+        fa.step()
+        fb.step()
+    U = int(host(fa.num_unique)[0])
+    np.testing.assert_array_equal(host(fa.row_grads)[:U], host(fb.row_grads)[:U])
+    assert torch.equal(fa.table, fb.table)          # whole table, compared on the device
