@@ -63,8 +63,37 @@ def stage_bytes(w, U):
     }
 
 
-# Stages that are one kernel launch each (a roofline needs one kernel's duration).
-SINGLE_KERNEL = {"embbag_fwd", "interaction_fwd", "interaction_bwd", "sparse_sgd", "gather_rows"}
+# Stages that are one kernel launch each (a roofline needs one kernel's duration), with the
+# kernel's name prefix and source file.
+SINGLE_KERNEL = {
+    "embbag_fwd": ("embbag_fwd_kernel", "embbag.hip"),
+    "interaction_fwd": ("interaction_fwd_", "interaction.hip"),
+    "interaction_bwd": ("interaction_bwd_", "interaction.hip"),
+    "sparse_sgd": ("sparse_sgd_kernel", "embbag.hip"),
+    "gather_rows": ("gather_rows_kernel", "embbag.hip"),
+}
+
+
+def measured_traffic(config: str, stage: str):
+    """HBM bytes per launch of the stage's kernel from the committed rocprofv3 counter runs
+    (FETCH_SIZE + WRITE_SIZE, each scaled by a plain copy of known size), or None when
+    there is no such run or the kernel's source changed since it was taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "hbm_traffic_%s.json" % config)
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        prof = json.load(f)
+    prefix, src = SINGLE_KERNEL[stage]
+    csrc = os.path.join(ROOT, "sparse_embedding_lookup_amd", "csrc")
+    for fname in (src, "ctr_internal.h"):
+        with open(os.path.join(csrc, fname), "rb") as f:
+            if hashlib.sha256(f.read()).hexdigest()[:16] != prof["source_sha256_16"].get(fname):
+                return None
+    for name, v in prof["per_launch"].items():
+        if prefix in name:
+            return v["fetch_bytes"] + v["write_bytes"]
+    return None
 
 
 def cpu_baseline(w, seconds: float):
@@ -134,6 +163,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--detail", default="", help="write per-stage detail JSON here")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MB",
+                    help="run one device copy of MB MiB first (scale for HBM byte counters)")
     ap.add_argument("--graph", action="store_true",
                     help="replay captured HIP graph segments instead of launching from the host")
     args = ap.parse_args()
@@ -153,6 +184,16 @@ def main():
     fe = FrontEnd(w, "cuda")
     st = fe.stages()
     torch.cuda.synchronize()
+    if args.copy_calibration:
+        # a plain copy of known size: its FETCH_SIZE / WRITE_SIZE counters calibrate the
+        # counter-measured traffic of the path's kernels
+        nb = args.copy_calibration << 20
+        src = torch.ones(nb // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     for _ in range(args.warmup):
         fe.step()
@@ -259,7 +300,9 @@ def main():
         "stage_ms": {k: round(v, 5) for k, v in stage_ms.items()},
         "roofline": {"kernel": dominant, "bound": "hbm", "achieved": achieved,
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
-                     "traffic": None, "bytes_per_launch": byts[dominant],
+                     "traffic": measured_traffic(args.config, dominant),
+                     "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE+WRITE_SIZE)",
+                     "bytes_per_launch": byts[dominant],
                      "avg_launch_ms": dom_ms},
     }
     if not args.no_cpu:

@@ -1,0 +1,275 @@
+"""Parity at the workloads' full sizes, in the configuration bench.py times (fused backward +
+SGD, unique on the side stream).
+
+Tiny, Small, Criteo and TensorNet run the whole step on both sides.  Large (65.5 GB of bf16
+tables, 67M occurrences) is checked on sampled outputs the oracle computes one by one
+(pooled bags, interaction rows of sampled samples, per-row gradients and updated rows of
+sampled keys) and on properties that hold at any size (unique/inverse/perm invariants against
+numpy.unique).
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import oracle as orc
+from sparse_embedding_lookup_amd import ctr, workloads
+from sparse_embedding_lookup_amd.pipeline import FrontEnd
+from tests.parity import RTOL_BF16, RTOL_F32, assert_close
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
+
+DEV = "cuda"
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def host(t):
+    torch.cuda.synchronize()
+    return t.detach().cpu().numpy()
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+
+
+def check_unique_properties(keys, fe):
+    """GPU unique outputs against numpy.unique and the invariants, at any size."""
+    n = keys.size
+    U = int(host(fe.num_unique)[0])
+    uniq = host(fe.uniq[:max(U, 1)])[:U]
+    inv = host(fe.inverse[:n])
+    perm = host(fe.perm[:n])
+    seg = host(fe.seg[:U + 1])
+    u2, cnt = np.unique(keys, return_counts=True)
+    assert U == u2.size
+    np.testing.assert_array_equal(uniq, u2)
+    np.testing.assert_array_equal(np.diff(seg), cnt)
+    np.testing.assert_array_equal(uniq[inv], keys)
+    sk = keys[perm]
+    d = np.diff(sk)
+    assert np.all(d >= 0)
+    assert np.all(np.diff(perm.astype(np.int64))[d == 0] > 0)      # stable
+    assert np.array_equal(np.bincount(perm, minlength=n), np.ones(n, np.int64))
+    return uniq, inv
+
+
+def oracle_dlrm(w):
+    tab = orc.Table(w.rows, w.dim, w.dtype, w.table_seed)
+    pooled, pmag = orc.embbag_fwd(tab, w.indices, w.offsets, w.batch)
+    B, F, d = w.batch, w.F, w.dim
+    Z = np.empty((B, F, d))
+    Zm = np.empty((B, F, d))
+    Z[:, 0] = w.dense
+    Zm[:, 0] = np.abs(w.dense)
+    Z[:, 1:] = pooled
+    Zm[:, 1:] = pmag
+    R, Rm = orc.interaction_fwd(Z, Zm)
+    dZ, dZm = orc.interaction_bwd(Z, w.grad_out.astype(np.float64), Zm)
+    keys = orc.form_keys(w.indices, w.offsets, w.num_tables, B, w.row_base)
+    uniq, inv, perm, seg = orc.unique(keys)
+    g, gm = orc.embbag_bwd(dZ[:, 1:], w.offsets, B, w.num_tables, inv, uniq.size, dZm[:, 1:])
+    new, nm = orc.sparse_sgd(tab, uniq, g, gm, w.lr)
+    return dict(Z=Z, Zm=Zm, R=R, Rm=Rm, dZ=dZ, dZm=dZm, keys=keys, uniq=uniq, inv=inv, g=g,
+                gm=gm, new=new, nm=nm)
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("name", ["tiny", "small", "criteo"])
+def test_full_dlrm_step(name):
+    w = workloads.make(name)
+    say("full step", name, "nnz", w.nnz)
+    fe = FrontEnd(w, DEV, keep_grads=True)
+    fe.step()
+    torch.cuda.synchronize()
+    say("oracle", name)
+    o = oracle_dlrm(w)
+    rt = RTOL_BF16 if w.compute == "bf16" else RTOL_F32
+    assert_close(host(fe.Z), o["Z"], o["Zm"], RTOL_F32, "Z")
+    assert_close(host(fe.R), o["R"], o["Rm"], 3 * rt, "R")
+    assert_close(host(fe.dZ), o["dZ"], o["dZm"], 3 * rt, "dZ")
+    uniq, inv = check_unique_properties(o["keys"], fe)
+    np.testing.assert_array_equal(uniq, o["uniq"])
+    np.testing.assert_array_equal(inv, o["inv"])
+    U = uniq.size
+    assert_close(host(fe.row_grads[:U]), o["g"], o["gm"], 4 * rt, "row grads")
+    rows = host(fe.table[dev(o["uniq"])].float())
+    assert_close(rows, o["new"], o["nm"], 4 * rt + (RTOL_BF16 if w.dtype == "bf16" else 0.0),
+                 "updated rows")
+    # rows outside the batch are untouched: compare a sample against the fill definition
+    rng = np.random.default_rng(5)
+    cand = rng.integers(0, w.total_rows, 4000)
+    cand = cand[~np.isin(cand, o["uniq"])][:2000]
+    tab = orc.Table(w.rows, w.dim, w.dtype, w.table_seed)
+    np.testing.assert_array_equal(host(fe.table[dev(cand)].float()), orc.table_rows(tab, cand))
+
+
+@pytest.mark.timeout(600)
+def test_full_tensornet_step():
+    w = workloads.tensornet()
+    say("full step tensornet nnz", w.nnz)
+    fe = FrontEnd(w, DEV, keep_grads=True)
+    fe.step()
+    torch.cuda.synchronize()
+    tab = orc.Table(w.rows, w.dim, w.dtype, w.table_seed)
+    keys = orc.form_keys(w.indices, w.offsets, 1, w.nnz, np.array([0, w.rows[0]]), w.key_modulus)
+    say("oracle unique")
+    uniq, inv, perm, seg = orc.unique(keys)
+    U = uniq.size
+    u_gpu, i_gpu = check_unique_properties(keys, fe)
+    np.testing.assert_array_equal(u_gpu, uniq)
+    np.testing.assert_array_equal(i_gpu, inv)
+    np.testing.assert_array_equal(host(fe.perm[:w.nnz]), perm)
+    E = orc.gather_rows(tab, uniq)
+    np.testing.assert_array_equal(host(fe.E[:U]), E)
+    out = host(fe.out[:w.nnz])
+    np.testing.assert_array_equal(out, E[inv])          # per-slot vectors: exact row copies
+    dout = w.grad_out.reshape(w.nnz, 1, w.dim).astype(np.float64)
+    g, gm = orc.embbag_bwd(dout, w.offsets, w.nnz, 1, inv, U)
+    assert_close(host(fe.row_grads[:U]), g, gm, RTOL_F32, "tensornet row grads")
+    new, nm = orc.sparse_sgd(tab, uniq, g, gm, w.lr)
+    assert_close(host(fe.table[dev(uniq)]), new, nm, 2 * RTOL_F32, "tensornet rows")
+
+
+@pytest.fixture(scope="module")
+def large_run():
+    say("generating Large")
+    w = workloads.large()
+    say("Large nnz", w.nnz)
+    fe = FrontEnd(w, DEV, keep_grads=True)
+    fe.step()
+    torch.cuda.synchronize()
+    say("Large step done")
+    yield w, fe
+    del fe
+    torch.cuda.empty_cache()
+
+
+def _sample_bags(w, k, seed):
+    rng = np.random.default_rng(seed)
+    return rng.choice(w.num_tables * w.batch, size=k, replace=False)
+
+
+@pytest.mark.timeout(900)
+def test_large_pooling_sampled(large_run):
+    w, fe = large_run
+    one = orc.Table(w.rows, w.dim, w.dtype, w.table_seed)   # rows regenerated by definition
+    Z = host(fe.Z)
+    for s in _sample_bags(w, 3000, 1):
+        t, b = divmod(int(s), w.batch)
+        lo, hi = int(w.offsets[s]), int(w.offsets[s + 1])
+        # the bag alone: a CSR with one bag per table, only table t's non-empty
+        off = np.zeros(w.num_tables + 1, dtype=np.int64)
+        off[t + 1:] = hi - lo
+        out, mag = orc.embbag_fwd(one, w.indices[lo:hi], off, 1)
+        assert_close(Z[b, 1 + t], out[0, t], mag[0, t], RTOL_F32, "Large pooled bag %d" % s)
+
+
+@pytest.mark.timeout(900)
+def test_large_interaction_sampled(large_run):
+    """Interaction rows of sampled samples: the oracle pools every table of those samples
+    itself, then runs the interaction forward and backward for them."""
+    w, fe = large_run
+    rng = np.random.default_rng(2)
+    samples = rng.choice(w.batch, size=24, replace=False)
+    one = orc.Table(w.rows, w.dim, w.dtype, w.table_seed)
+    R = host(fe.R)
+    dZ = host(fe.dZ)
+    for b in samples:
+        ids, lens = [], []
+        for t in range(w.num_tables):
+            s = t * w.batch + int(b)
+            ids.append(w.indices[w.offsets[s]:w.offsets[s + 1]])
+            lens.append(int(w.offsets[s + 1] - w.offsets[s]))
+        off = np.zeros(w.num_tables + 1, dtype=np.int64)
+        off[1:] = np.cumsum(lens)
+        pooled, pmag = orc.embbag_fwd(one, np.concatenate(ids), off, 1)
+        Z = np.concatenate([w.dense[b][None, None, :].astype(np.float64), pooled], axis=1)
+        Zm = np.concatenate([np.abs(w.dense[b])[None, None, :].astype(np.float64), pmag], axis=1)
+        Rw, Rm = orc.interaction_fwd(Z, Zm)
+        assert_close(R[b][None], Rw, Rm, 3 * RTOL_BF16, "Large R sample %d" % b)
+        dZw, dZm = orc.interaction_bwd(Z, w.grad_out[b][None].astype(np.float64), Zm)
+        assert_close(dZ[b][None], dZw, dZm, 3 * RTOL_BF16, "Large dZ sample %d" % b)
+
+
+@pytest.mark.timeout(900)
+def test_large_unique_properties(large_run):
+    w, fe = large_run
+    keys = orc.form_keys(w.indices, w.offsets, w.num_tables, w.batch, w.row_base)
+    check_unique_properties(keys, fe)
+
+
+@pytest.mark.timeout(900)
+def test_large_backward_sampled(large_run):
+    """Per-call parity of the backward at full size with GPU-independent inputs: the
+    generator's N(0,1) gradient for every bag, reduced with the step's own grouping, checked
+    on sampled rows (hot and cold) that the oracle sums over their occurrences."""
+    w, fe = large_run
+    rng = np.random.default_rng(3)
+    B, T, d = w.batch, w.num_tables, w.dim
+    dY = rng.standard_normal((B, T, d)).astype(np.float32)
+    keys = orc.form_keys(w.indices, w.offsets, T, B, w.row_base)
+    g_gpu = ctr.ctr_embbag_bwd(dev(dY), T * d, d, fe.offsets, B, T, d, None, None,
+                               fe.num_unique, row_grads=fe.row_grads, sorted_src=fe.sorted_src,
+                               nnz=w.nnz, workspace=fe.ws_bwd)
+    U = int(host(fe.num_unique)[0])
+    uniq = host(fe.uniq[:U])
+    # sample distinct rows: the hottest ones and random ones
+    counts = np.bincount(np.searchsorted(uniq, keys), minlength=U)
+    pick = np.concatenate([np.argsort(-counts)[:20], rng.choice(U, 300, replace=False)])
+    pick = np.unique(pick)
+    occ = np.flatnonzero(np.isin(keys, uniq[pick]))
+    bag = np.searchsorted(w.offsets, occ, side="right") - 1
+    sub_inv = np.searchsorted(uniq[pick], keys[occ]).astype(np.int32)
+    # the selected occurrences as one-occurrence bags over a [len(occ), 1, d] gradient
+    sel = dY[bag % B, bag // B].astype(np.float64)[:, None, :]
+    g, gm = orc.embbag_bwd(sel, np.arange(occ.size + 1, dtype=np.int64), occ.size, 1, sub_inv,
+                           pick.size)
+    got = host(g_gpu[dev(pick.astype(np.int64))])
+    assert_close(got, g, gm, RTOL_F32, "Large row grads")
+
+
+@pytest.mark.timeout(900)
+def test_large_sgd_sampled(large_run):
+    """Updated rows of sampled keys: the oracle recomputes those rows' gradients over their
+    occurrences from its own interaction backward of the samples involved."""
+    w, fe = large_run
+    rng = np.random.default_rng(4)
+    U = int(host(fe.num_unique)[0])
+    uniq = host(fe.uniq[:U])
+    keys = orc.form_keys(w.indices, w.offsets, w.num_tables, w.batch, w.row_base)
+    counts = np.bincount(np.searchsorted(uniq, keys), minlength=U)
+    cold = np.flatnonzero(counts <= 2)
+    pick = np.unique(rng.choice(cold, 40, replace=False))   # rows with few occurrences
+    occ = np.flatnonzero(np.isin(keys, uniq[pick]))
+    bag = np.searchsorted(w.offsets, occ, side="right") - 1
+    one = orc.Table(w.rows, w.dim, w.dtype, w.table_seed)
+    g = np.zeros((pick.size, w.dim))
+    gm = np.zeros((pick.size, w.dim))
+    cache = {}
+    for o, s in zip(occ, bag):
+        t, b = divmod(int(s), w.batch)
+        if b not in cache:
+            ids, lens = [], []
+            for tt in range(w.num_tables):
+                ss = tt * w.batch + b
+                ids.append(w.indices[w.offsets[ss]:w.offsets[ss + 1]])
+                lens.append(int(w.offsets[ss + 1] - w.offsets[ss]))
+            off = np.zeros(w.num_tables + 1, dtype=np.int64)
+            off[1:] = np.cumsum(lens)
+            pooled, pmag = orc.embbag_fwd(one, np.concatenate(ids), off, 1)
+            Z = np.concatenate([w.dense[b][None, None, :].astype(np.float64), pooled], axis=1)
+            Zm = np.concatenate([np.abs(w.dense[b])[None, None, :].astype(np.float64), pmag], axis=1)
+            cache[b] = orc.interaction_bwd(Z, w.grad_out[b][None].astype(np.float64), Zm)
+        dZ, dZm = cache[b]
+        k = np.searchsorted(uniq[pick], keys[o])
+        g[k] += dZ[0, 1 + t]
+        gm[k] += dZm[0, 1 + t]
+    new, nm = orc.sparse_sgd(one, uniq[pick], g, gm, w.lr)
+    got = host(fe.table[dev(uniq[pick])].float())
+    assert_close(got, new, nm, 4 * RTOL_BF16 + RTOL_BF16, "Large updated rows")
