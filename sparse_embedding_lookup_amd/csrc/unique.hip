@@ -25,9 +25,8 @@ namespace ctr {
 namespace {
 
 constexpr int kThreads = 256;                 // 4 waves
-constexpr int kItems = 8;                     // keys per thread per tile
-constexpr int kTile = kThreads * kItems;      // 2048 keys per tile
 constexpr int kMaxBits = 8;                   // widest digit (wider digits scatter worse)
+constexpr int kBuckets = 1 << kMaxBits;
 constexpr int kMaxBlocks = 1024;              // radix blocks (ranges) per pass
 constexpr int kFinTile = 2048;                // positions per finalize block
 
@@ -81,15 +80,14 @@ __device__ __forceinline__ int64_t floor_mod(int64_t id, int64_t m) {
 }
 
 // --------------------------------------------------------------------------- a1: keys
-// Bags known: one wave per 64 consecutive bags; lane l holds the end of bag s0 + l and every
-// occurrence finds its bag by a 6-step binary search over those ends (shuffles).
-// `parts` waves share one group of 64 bags, each taking every parts-th stretch of 64
-// occurrences, so long bags still spread over enough waves to fill the chip.
-template <bool ID64>
+// Bags known: `parts` waves share one group of 64 consecutive bags; lane l holds the end of
+// bag s0 + l and every occurrence finds its bag by a 6-step binary search over those ends
+// (shuffles); each wave takes every parts-th stretch of 64 occurrences of the group.
+template <bool ID64, typename K>
 __global__ __launch_bounds__(kThreads) void form_keys_bags_kernel(
     const void* __restrict__ ids, int64_t n, const int64_t* __restrict__ offsets, int64_t batch,
     int64_t num_bags, const int64_t* __restrict__ row_base, int64_t modulus, uint64_t flip,
-    int parts, uint64_t* __restrict__ keys, uint32_t* __restrict__ bags) {
+    int parts, K* __restrict__ keys, uint32_t* __restrict__ bags) {
   const int lane = threadIdx.x & 63;
   const int64_t wave = ((int64_t)blockIdx.x * kThreads + threadIdx.x) >> 6;
   const int64_t s0 = (wave / parts) * 64;
@@ -114,34 +112,35 @@ __global__ __launch_bounds__(kThreads) void form_keys_bags_kernel(
                               : (int64_t) static_cast<const int32_t*>(ids)[i];
       int64_t key = floor_mod(id, modulus);
       if (row_base) key += row_base[bag / batch];
-      keys[i] = (uint64_t)key ^ flip;
+      keys[i] = (K)((uint64_t)key ^ flip);
       bags[i] = (uint32_t)bag;
     }
   }
 }
 
 // No bags: each occurrence is its own bag.
-template <bool ID64>
+template <bool ID64, typename K>
 __global__ __launch_bounds__(kThreads) void form_keys_flat_kernel(const void* __restrict__ ids,
                                                                   int64_t n, int64_t modulus,
                                                                   uint64_t flip,
-                                                                  uint64_t* __restrict__ keys) {
+                                                                  K* __restrict__ keys) {
   const int64_t stride = (int64_t)gridDim.x * kThreads;
   for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n; i += stride) {
     const int64_t id = ID64 ? static_cast<const int64_t*>(ids)[i]
                             : (int64_t) static_cast<const int32_t*>(ids)[i];
-    keys[i] = (uint64_t)floor_mod(id, modulus) ^ flip;
+    keys[i] = (K)((uint64_t)floor_mod(id, modulus) ^ flip);
   }
 }
 
 // --------------------------------------------------------------------------- upsweep
-template <int NB>
+// Digit counts of each block's contiguous range; hist is block-major: hist[block][digit].
+template <typename K>
 __global__ __launch_bounds__(kThreads) void radix_upsweep_kernel(
-    const uint64_t* __restrict__ keys, int64_t n, int shift, int nbits, int64_t per_block,
-    uint32_t* __restrict__ hist, int nblocks) {
-  __shared__ uint32_t cnt[4][NB];
+    const K* __restrict__ keys, int64_t n, int shift, int nbits, int64_t per_block,
+    uint32_t* __restrict__ hist) {
+  __shared__ uint32_t cnt[4][kBuckets];
   const int wave = threadIdx.x >> 6;
-  for (int i = threadIdx.x; i < 4 * NB; i += kThreads) (&cnt[0][0])[i] = 0;
+  for (int i = threadIdx.x; i < 4 * kBuckets; i += kThreads) (&cnt[0][0])[i] = 0;
   __syncthreads();
   const uint32_t mask = (1u << nbits) - 1u;
   const int64_t beg = (int64_t)blockIdx.x * per_block;
@@ -156,91 +155,84 @@ __global__ __launch_bounds__(kThreads) void radix_upsweep_kernel(
     if (valid && (m & lt) == 0) cnt[wave][d] += (uint32_t)__popcll(m);
   }
   __syncthreads();
-  for (int d = threadIdx.x; d < NB; d += kThreads)
-    hist[(int64_t)d * nblocks + blockIdx.x] = cnt[0][d] + cnt[1][d] + cnt[2][d] + cnt[3][d];
+  const int d = threadIdx.x;
+  hist[(int64_t)blockIdx.x * kBuckets + d] = cnt[0][d] + cnt[1][d] + cnt[2][d] + cnt[3][d];
 }
 
 // --------------------------------------------------------------------------- scan
-// Block d: exclusive scan of hist[d][0..nblocks) in place, totals[d] = row sum.
+// Many blocks: block d scans digit d's counts over the blocks (exclusive, in place) and
+// stores the digit total.  (With few blocks the downsweep does this itself.)
 __global__ __launch_bounds__(kThreads) void radix_scan_kernel(uint32_t* __restrict__ hist,
                                                               int nblocks,
                                                               uint32_t* __restrict__ totals) {
   __shared__ uint32_t tmp[4];
-  uint32_t* row = hist + (int64_t)blockIdx.x * nblocks;
+  const int d = blockIdx.x;
   const int per = (nblocks + kThreads - 1) / kThreads;   // <= 4
   const int b0 = threadIdx.x * per;
   uint32_t local[4] = {0, 0, 0, 0};
   uint32_t sum = 0;
   for (int j = 0; j < per; ++j) {
     const int k = b0 + j;
-    local[j] = k < nblocks ? row[k] : 0u;
+    local[j] = k < nblocks ? hist[(int64_t)k * kBuckets + d] : 0u;
     sum += local[j];
   }
   uint32_t total;
   uint32_t run = block_excl_scan_256(sum, tmp, &total);
   for (int j = 0; j < per; ++j) {
     const int k = b0 + j;
-    if (k < nblocks) row[k] = run;
+    if (k < nblocks) hist[(int64_t)k * kBuckets + d] = run;
     run += local[j];
   }
-  if (threadIdx.x == 0) totals[blockIdx.x] = total;
+  if (threadIdx.x == 0) totals[d] = total;
 }
 
 // --------------------------------------------------------------------------- downsweep
-template <int NB>
+template <typename K, int ITEMS>
 struct DownsweepSmem {
-  uint64_t keys[kTile];
-  uint32_t vals[kTile];
-  uint32_t bags[kTile];
-  uint32_t wcnt[4][NB];
-  uint32_t run[NB];
-  uint32_t tstart[NB];
-  uint32_t tcount[NB];
+  K keys[kThreads * ITEMS];
+  uint32_t vals[kThreads * ITEMS];
+  uint32_t bags[kThreads * ITEMS];
+  uint32_t wcnt[4][kBuckets];
+  uint32_t run[kBuckets];
+  uint32_t tstart[kBuckets];
+  uint32_t tcount[kBuckets];
   uint32_t tmp[4];
 };
 
-// Exclusive scan over NB per-digit values held in LDS `a` (in place); returns nothing,
-// every thread must call it.  Thread t owns digits [t*DPT, (t+1)*DPT).
-template <int NB>
-__device__ __forceinline__ void lds_excl_scan(uint32_t* a, uint32_t* tmp) {
-  constexpr int DPT = NB / kThreads;
-  uint32_t v[DPT];
-  uint32_t s = 0;
-#pragma unroll
-  for (int j = 0; j < DPT; ++j) {
-    v[j] = a[threadIdx.x * DPT + j];
-    s += v[j];
-  }
-  uint32_t total;
-  uint32_t run = block_excl_scan_256(s, tmp, &total);
-#pragma unroll
-  for (int j = 0; j < DPT; ++j) {
-    a[threadIdx.x * DPT + j] = run;
-    run += v[j];
-  }
-}
-
-// IDENT: payload of pass 0 is the element index.  BAGS: a second payload (the bag) rides along.
-template <int NB, bool IDENT, bool BAGS>
+// IDENT: payload of pass 0 is the element index.  BAGS: a second payload (the bag) rides
+// along.  FUSED: few blocks, so this block sums the digit counts of the blocks before it
+// itself instead of reading a separate scan's output.
+template <typename K, int ITEMS, bool IDENT, bool BAGS, bool FUSED>
 __global__ __launch_bounds__(kThreads) void radix_downsweep_kernel(
-    const uint64_t* __restrict__ keys_in, const uint32_t* __restrict__ vals_in,
-    const uint32_t* __restrict__ bags_in, uint64_t* __restrict__ keys_out,
+    const K* __restrict__ keys_in, const uint32_t* __restrict__ vals_in,
+    const uint32_t* __restrict__ bags_in, K* __restrict__ keys_out,
     uint32_t* __restrict__ vals_out, uint32_t* __restrict__ bags_out, int64_t n, int shift,
     int nbits, int64_t per_block, const uint32_t* __restrict__ hist,
     const uint32_t* __restrict__ totals, int nblocks) {
-  __shared__ DownsweepSmem<NB> sm;
-  constexpr int DPT = NB / kThreads;
+  constexpr int kT = kThreads * ITEMS;
+  __shared__ DownsweepSmem<K, ITEMS> sm;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const uint32_t mask = (1u << nbits) - 1u;
 
-  // Global start of each digit for this block: digits before it, then blocks before it.
-  for (int j = 0; j < DPT; ++j) sm.run[threadIdx.x * DPT + j] = totals[threadIdx.x * DPT + j];
-  __syncthreads();
-  lds_excl_scan<NB>(sm.run, sm.tmp);
-  __syncthreads();
-  for (int j = 0; j < DPT; ++j) {
-    const int d = threadIdx.x * DPT + j;
-    sm.run[d] += hist[(int64_t)d * nblocks + blockIdx.x];
+  // Global start of each digit for this block: all digits before it, then the same digit in
+  // the blocks before it.
+  {
+    const int d = threadIdx.x;
+    uint32_t tot, before;
+    if (FUSED) {
+      tot = 0;
+      before = 0;
+      for (int g = 0; g < nblocks; ++g) {
+        const uint32_t c = hist[(int64_t)g * kBuckets + d];
+        tot += c;
+        if (g < (int)blockIdx.x) before += c;
+      }
+    } else {
+      tot = totals[d];
+      before = hist[(int64_t)blockIdx.x * kBuckets + d];
+    }
+    uint32_t all;
+    sm.run[d] = block_excl_scan_256(tot, sm.tmp, &all) + before;
   }
   __syncthreads();
 
@@ -248,24 +240,24 @@ __global__ __launch_bounds__(kThreads) void radix_downsweep_kernel(
   const int64_t end = beg + per_block < n ? beg + per_block : n;
   const uint64_t lt = lanemask_lt();
 
-  for (int64_t tile = beg; tile < end; tile += kTile) {
-    uint64_t key[kItems];
-    uint32_t val[kItems];
-    uint32_t bag[kItems];
-    uint32_t rank[kItems];
-    bool valid[kItems];
+  for (int64_t tile = beg; tile < end; tile += kT) {
+    K key[ITEMS];
+    uint32_t val[ITEMS];
+    uint32_t bag[ITEMS];
+    uint32_t rank[ITEMS];
+    bool valid[ITEMS];
 #pragma unroll
-    for (int k = 0; k < kItems; ++k) {
-      const int64_t e = tile + (int64_t)wave * 64 * kItems + k * 64 + lane;
+    for (int k = 0; k < ITEMS; ++k) {
+      const int64_t e = tile + (int64_t)wave * 64 * ITEMS + k * 64 + lane;
       valid[k] = e < end;
-      key[k] = valid[k] ? keys_in[e] : 0ull;
+      key[k] = valid[k] ? keys_in[e] : (K)0;
       val[k] = valid[k] ? (IDENT ? (uint32_t)e : vals_in[e]) : 0u;
       bag[k] = (BAGS && valid[k]) ? bags_in[e] : 0u;
     }
-    for (int d = lane; d < NB; d += 64) sm.wcnt[wave][d] = 0;
+    for (int d = lane; d < kBuckets; d += 64) sm.wcnt[wave][d] = 0;
     __builtin_amdgcn_wave_barrier();
 #pragma unroll
-    for (int k = 0; k < kItems; ++k) {
+    for (int k = 0; k < ITEMS; ++k) {
       const uint32_t d = (uint32_t)(key[k] >> shift) & mask;
       const uint64_t active = __ballot(valid[k]);
       const uint64_t m = match_digit(d, nbits, active);
@@ -278,23 +270,22 @@ __global__ __launch_bounds__(kThreads) void radix_downsweep_kernel(
       rank[k] = pre + r;
     }
     __syncthreads();
-#pragma unroll
-    for (int j = 0; j < DPT; ++j) {
-      const int d = threadIdx.x * DPT + j;
+    {
+      const int d = threadIdx.x;
       const uint32_t c0 = sm.wcnt[0][d], c1 = sm.wcnt[1][d], c2 = sm.wcnt[2][d],
                      c3 = sm.wcnt[3][d];
       sm.wcnt[0][d] = 0;
       sm.wcnt[1][d] = c0;
       sm.wcnt[2][d] = c0 + c1;
       sm.wcnt[3][d] = c0 + c1 + c2;
-      sm.tcount[d] = c0 + c1 + c2 + c3;
-      sm.tstart[d] = c0 + c1 + c2 + c3;
+      const uint32_t cnt = c0 + c1 + c2 + c3;
+      sm.tcount[d] = cnt;
+      uint32_t all;
+      sm.tstart[d] = block_excl_scan_256(cnt, sm.tmp, &all);
     }
     __syncthreads();
-    lds_excl_scan<NB>(sm.tstart, sm.tmp);
-    __syncthreads();
 #pragma unroll
-    for (int k = 0; k < kItems; ++k) {
+    for (int k = 0; k < ITEMS; ++k) {
       if (valid[k]) {
         const uint32_t d = (uint32_t)(key[k] >> shift) & mask;
         const uint32_t pos = sm.tstart[d] + sm.wcnt[wave][d] + rank[k];
@@ -304,9 +295,9 @@ __global__ __launch_bounds__(kThreads) void radix_downsweep_kernel(
       }
     }
     __syncthreads();
-    const int tile_n = (int)((end - tile) < kTile ? (end - tile) : kTile);
+    const int tile_n = (int)((end - tile) < kT ? (end - tile) : kT);
     for (int q = threadIdx.x; q < tile_n; q += kThreads) {
-      const uint64_t kk = sm.keys[q];
+      const K kk = sm.keys[q];
       const uint32_t d = (uint32_t)(kk >> shift) & mask;
       const uint32_t o = sm.run[d] + (uint32_t)q - sm.tstart[d];
       keys_out[o] = kk;
@@ -314,8 +305,7 @@ __global__ __launch_bounds__(kThreads) void radix_downsweep_kernel(
       if (BAGS) bags_out[o] = sm.bags[q];
     }
     __syncthreads();
-#pragma unroll
-    for (int j = 0; j < DPT; ++j) sm.run[threadIdx.x * DPT + j] += sm.tcount[threadIdx.x * DPT + j];
+    sm.run[threadIdx.x] += sm.tcount[threadIdx.x];
     __syncthreads();
   }
 }
@@ -325,15 +315,17 @@ __global__ __launch_bounds__(kThreads) void radix_downsweep_kernel(
 // every load and store is coalesced; a head is a position whose key differs from the one
 // before, and ranks come from wave ballots (popcount of the heads before a lane).
 constexpr int kFinRounds = kFinTile / kThreads;     // 8
+constexpr int kFusedHeadTiles = 1024;               // up to this many tiles, no scan kernel
 
-__device__ __forceinline__ bool is_head(const uint64_t* __restrict__ sk, int64_t p, int64_t n,
-                                        uint64_t* key) {
+template <typename K>
+__device__ __forceinline__ bool is_head(const K* __restrict__ sk, int64_t p, int64_t n, K* key) {
   if (p >= n) return false;
   *key = sk[p];
   return p == 0 || *key != sk[p - 1];
 }
 
-__global__ __launch_bounds__(kThreads) void heads_count_kernel(const uint64_t* __restrict__ sk,
+template <typename K>
+__global__ __launch_bounds__(kThreads) void heads_count_kernel(const K* __restrict__ sk,
                                                                int64_t n,
                                                                uint32_t* __restrict__ tile_heads) {
   __shared__ uint32_t wsum[4];
@@ -342,7 +334,7 @@ __global__ __launch_bounds__(kThreads) void heads_count_kernel(const uint64_t* _
   uint32_t c = 0;
 #pragma unroll
   for (int j = 0; j < kFinRounds; ++j) {
-    uint64_t k;
+    K k;
     const bool h = is_head(sk, t0 + (int64_t)j * kThreads + threadIdx.x, n, &k);
     c += (uint32_t)__popcll(__ballot(h));
   }
@@ -389,21 +381,49 @@ __global__ __launch_bounds__(1024) void heads_scan_kernel(uint32_t* __restrict__
 }
 
 // sorted_src[p] = (distinct-row index of position p, bag of its occurrence); without bags
-// the occurrence is its own bag.
+// the occurrence is its own bag.  FUSED: the block sums the head counts of the tiles before
+// it itself (few tiles), and the last block publishes U.
+template <typename K, bool FUSED>
 __global__ __launch_bounds__(kThreads) void unique_finalize_kernel(
-    const uint64_t* __restrict__ sk, const uint32_t* __restrict__ sv,
-    const uint32_t* __restrict__ sbag, int64_t n, uint64_t flip,
-    const uint32_t* __restrict__ tile_heads, int64_t* __restrict__ uniq,
-    int32_t* __restrict__ inverse, int32_t* __restrict__ seg_offsets,
-    int2* __restrict__ sorted_src) {
+    const K* __restrict__ sk, const uint32_t* __restrict__ sv, const uint32_t* __restrict__ sbag,
+    int64_t n, uint64_t flip, const uint32_t* __restrict__ tile_heads, int64_t ntiles,
+    int64_t* __restrict__ uniq, int32_t* __restrict__ inverse, int32_t* __restrict__ seg_offsets,
+    int2* __restrict__ sorted_src, int32_t* __restrict__ num_unique) {
   __shared__ uint32_t wsum[4];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const uint64_t le = (lane == 63) ? ~0ull : ((2ull << lane) - 1ull);
   const int64_t t0 = (int64_t)blockIdx.x * kFinTile;
-  uint32_t base = tile_heads[blockIdx.x];         // heads before this tile
+  uint32_t base;                                  // heads before this tile
+  if (FUSED) {
+    uint32_t s = 0, all = 0;
+    for (int64_t t = threadIdx.x; t < ntiles; t += kThreads) {
+      const uint32_t c = tile_heads[t];
+      all += c;
+      if (t < (int64_t)blockIdx.x) s += c;
+    }
+    // block sums of s and all
+    for (int o = 32; o > 0; o >>= 1) {
+      s += __shfl_xor(s, o, 64);
+      all += __shfl_xor(all, o, 64);
+    }
+    if (lane == 0) wsum[wave] = s;
+    __syncthreads();
+    base = wsum[0] + wsum[1] + wsum[2] + wsum[3];
+    __syncthreads();
+    if (lane == 0) wsum[wave] = all;
+    __syncthreads();
+    const uint32_t tot = wsum[0] + wsum[1] + wsum[2] + wsum[3];
+    __syncthreads();
+    if (blockIdx.x == gridDim.x - 1 && threadIdx.x == 0) {
+      *num_unique = (int32_t)tot;
+      if (seg_offsets) seg_offsets[tot] = (int32_t)n;
+    }
+  } else {
+    base = tile_heads[blockIdx.x];
+  }
   for (int j = 0; j < kFinRounds; ++j) {
     const int64_t p = t0 + (int64_t)j * kThreads + threadIdx.x;
-    uint64_t k = 0;
+    K k = 0;
     const bool h = is_head(sk, p, n, &k);
     const uint64_t m = __ballot(h);
     if (lane == 0) wsum[wave] = (uint32_t)__popcll(m);
@@ -415,7 +435,7 @@ __global__ __launch_bounds__(kThreads) void unique_finalize_kernel(
     if (p < n) {
       const uint32_t r = before + (uint32_t)__popcll(m & le) - 1u;   // heads <= p, minus one
       if (h) {
-        uniq[r] = (int64_t)(k ^ flip);
+        uniq[r] = (int64_t)((uint64_t)k ^ flip);
         if (seg_offsets) seg_offsets[r] = (int32_t)p;
       }
       const uint32_t occ = sv[p];
@@ -436,8 +456,8 @@ __global__ void unique_empty_kernel(int32_t* num_unique, int32_t* seg_offsets) {
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct UniqueWs {
-  uint64_t* keys_a;
-  uint64_t* keys_b;
+  void* keys_a;
+  void* keys_b;
   uint32_t* vals_a;
   uint32_t* vals_b;
   uint32_t* bags_a;
@@ -457,39 +477,145 @@ UniqueWs carve(void* base, int64_t n) {
     off += align256(sz);
     return p;
   };
-  w.keys_a = reinterpret_cast<uint64_t*>(take(sizeof(uint64_t) * (size_t)n));
-  w.keys_b = reinterpret_cast<uint64_t*>(take(sizeof(uint64_t) * (size_t)n));
+  w.keys_a = take(sizeof(uint64_t) * (size_t)n);
+  w.keys_b = take(sizeof(uint64_t) * (size_t)n);
   w.vals_a = reinterpret_cast<uint32_t*>(take(sizeof(uint32_t) * (size_t)n));
   w.vals_b = reinterpret_cast<uint32_t*>(take(sizeof(uint32_t) * (size_t)n));
   w.bags_a = reinterpret_cast<uint32_t*>(take(sizeof(uint32_t) * (size_t)n));
   w.bags_b = reinterpret_cast<uint32_t*>(take(sizeof(uint32_t) * (size_t)n));
-  w.hist = reinterpret_cast<uint32_t*>(take(sizeof(uint32_t) * (1 << kMaxBits) * kMaxBlocks));
-  w.totals = reinterpret_cast<uint32_t*>(take(sizeof(uint32_t) * (1 << kMaxBits)));
+  w.hist = reinterpret_cast<uint32_t*>(take(sizeof(uint32_t) * kBuckets * kMaxBlocks));
+  w.totals = reinterpret_cast<uint32_t*>(take(sizeof(uint32_t) * kBuckets));
   w.tile_heads = reinterpret_cast<uint32_t*>(
       take(sizeof(uint32_t) * (size_t)((n + kFinTile - 1) / kFinTile + 1)));
   w.bytes = off;
   return w;
 }
 
-template <int NB>
-void radix_pass(bool first, bool bags, const uint64_t* kin, const uint32_t* vin,
-                const uint32_t* bin, uint64_t* kout, uint32_t* vout, uint32_t* bout, int64_t n,
-                int shift, int nbits, int64_t per_block, uint32_t* hist, uint32_t* totals,
-                int nblocks, hipStream_t s) {
-  radix_upsweep_kernel<NB><<<nblocks, kThreads, 0, s>>>(kin, n, shift, nbits, per_block, hist,
-                                                        nblocks);
-  radix_scan_kernel<<<NB, kThreads, 0, s>>>(hist, nblocks, totals);
-#define CTR_DS(I, B)                                                                         \
-  radix_downsweep_kernel<NB, I, B><<<nblocks, kThreads, 0, s>>>(kin, vin, bin, kout, vout,   \
-                                                                bout, n, shift, nbits,       \
-                                                                per_block, hist, totals,     \
-                                                                nblocks)
+template <typename K, int ITEMS>
+void radix_pass(bool first, bool bags, const K* kin, const uint32_t* vin, const uint32_t* bin,
+                K* kout, uint32_t* vout, uint32_t* bout, int64_t n, int shift, int nbits,
+                int64_t per_block, uint32_t* hist, uint32_t* totals, int nblocks,
+                hipStream_t s) {
+  radix_upsweep_kernel<K><<<nblocks, kThreads, 0, s>>>(kin, n, shift, nbits, per_block, hist);
+  const bool fused = nblocks <= kThreads;
+  if (!fused) radix_scan_kernel<<<kBuckets, kThreads, 0, s>>>(hist, nblocks, totals);
+#define CTR_DS(I, B, FU)                                                                   \
+  radix_downsweep_kernel<K, ITEMS, I, B, FU><<<nblocks, kThreads, 0, s>>>(                 \
+      kin, vin, bin, kout, vout, bout, n, shift, nbits, per_block, hist, totals, nblocks)
+#define CTR_DS2(I, B) \
+  if (fused) CTR_DS(I, B, true); else CTR_DS(I, B, false)
   if (first) {
-    if (bags) CTR_DS(true, true); else CTR_DS(true, false);
+    if (bags) { CTR_DS2(true, true); } else { CTR_DS2(true, false); }
   } else {
-    if (bags) CTR_DS(false, true); else CTR_DS(false, false);
+    if (bags) { CTR_DS2(false, true); } else { CTR_DS2(false, false); }
   }
+#undef CTR_DS2
 #undef CTR_DS
+}
+
+template <typename K, int ITEMS>
+void radix_sort(int key_bits, bool bags, K* keys_a, K* keys_b, uint32_t* vbuf0, uint32_t* vbuf1,
+                uint32_t* bags_a, uint32_t* bags_b, int64_t n, uint32_t* hist, uint32_t* totals,
+                const K** sk, const uint32_t** sv, const uint32_t** sb, hipStream_t s) {
+  constexpr int kT = kThreads * ITEMS;
+  const int64_t ntiles = (n + kT - 1) / kT;
+  int nblocks = (int)(ntiles < kMaxBlocks ? ntiles : kMaxBlocks);
+  const int64_t tiles_per_block = (ntiles + nblocks - 1) / nblocks;
+  nblocks = (int)((ntiles + tiles_per_block - 1) / tiles_per_block);
+  const int64_t per_block = tiles_per_block * kT;
+  const int passes = (key_bits + kMaxBits - 1) / kMaxBits;
+  K* kin = keys_a;
+  K* kout = keys_b;
+  uint32_t* vb[2] = {vbuf0, vbuf1};
+  const uint32_t* vin = nullptr;
+  uint32_t* bin = bags_a;
+  uint32_t* bout = bags_b;
+  int shift = 0;
+  for (int p = 0; p < passes; ++p) {
+    const int left = key_bits - shift;
+    const int nbits = (left + (passes - p) - 1) / (passes - p);   // spread bits evenly
+    uint32_t* vout = vb[(passes - 1 - p) & 1];                       // last pass -> vbuf0
+    radix_pass<K, ITEMS>(p == 0, bags, kin, vin, bin, kout, vout, bout, n, shift, nbits,
+                         per_block, hist, totals, nblocks, s);
+    shift += nbits;
+    vin = vout;
+    std::swap(kin, kout);
+    std::swap(bin, bout);
+  }
+  *sk = kin;
+  *sv = vin;
+  *sb = bags ? bin : nullptr;
+}
+
+template <typename K>
+hipError_t unique_impl(const void* ids, bool ids64, int64_t n, const int64_t* offsets,
+                       int64_t batch, int32_t num_tables, const int64_t* row_base,
+                       int64_t modulus, int key_bits, uint64_t flip, int64_t* uniq,
+                       int32_t* inverse, int32_t* num_unique, int32_t* perm,
+                       int32_t* seg_offsets, int2* sorted_src, UniqueWs& w, hipStream_t s) {
+  const bool bags = offsets != nullptr && sorted_src != nullptr;
+  K* keys_a = static_cast<K*>(w.keys_a);
+  K* keys_b = static_cast<K*>(w.keys_b);
+
+  // a1: keys (and bags)
+  if (offsets) {
+    const int64_t num_bags = (int64_t)num_tables * batch;
+    const int64_t groups = (num_bags + 63) / 64;
+    // about 4096 waves, but no part shorter than one 64-occurrence stretch
+    int64_t parts = (4096 + groups - 1) / groups;
+    const int64_t stretches = (n / (groups > 0 ? groups : 1) + 63) / 64;
+    if (parts > stretches) parts = stretches;
+    if (parts < 1) parts = 1;
+    const int64_t blocks = (groups * parts + 3) / 4;
+    if (blocks > 0) {
+      if (ids64)
+        form_keys_bags_kernel<true, K><<<(unsigned)blocks, kThreads, 0, s>>>(
+            ids, n, offsets, batch, num_bags, row_base, modulus, flip, (int)parts, keys_a,
+            w.bags_a);
+      else
+        form_keys_bags_kernel<false, K><<<(unsigned)blocks, kThreads, 0, s>>>(
+            ids, n, offsets, batch, num_bags, row_base, modulus, flip, (int)parts, keys_a,
+            w.bags_a);
+    }
+  } else {
+    int64_t blocks = (n + kThreads - 1) / kThreads;
+    if (blocks > 8192) blocks = 8192;
+    if (ids64)
+      form_keys_flat_kernel<true, K><<<(unsigned)blocks, kThreads, 0, s>>>(ids, n, modulus,
+                                                                           flip, keys_a);
+    else
+      form_keys_flat_kernel<false, K><<<(unsigned)blocks, kThreads, 0, s>>>(ids, n, modulus,
+                                                                            flip, keys_a);
+  }
+
+  // a2: stable LSD radix sort of (key, occurrence[, bag]) over the live key bits; values
+  // ping-pong so that the last pass lands in `perm` when the caller wants it.
+  uint32_t* vbuf0 = perm ? reinterpret_cast<uint32_t*>(perm) : w.vals_a;
+  uint32_t* vbuf1 = perm ? w.vals_a : w.vals_b;
+  const K* sk;
+  const uint32_t* sv;
+  const uint32_t* sb;
+  if (n <= (1 << 20))   // small batches: shorter tiles, more blocks, shorter chains
+    radix_sort<K, 4>(key_bits, bags, keys_a, keys_b, vbuf0, vbuf1, w.bags_a, w.bags_b, n,
+                     w.hist, w.totals, &sk, &sv, &sb, s);
+  else
+    radix_sort<K, 8>(key_bits, bags, keys_a, keys_b, vbuf0, vbuf1, w.bags_a, w.bags_b, n,
+                     w.hist, w.totals, &sk, &sv, &sb, s);
+
+  // finalize: heads, their scan, and the scatter of uniq / seg / inverse / sorted_src
+  const int64_t ftiles = (n + kFinTile - 1) / kFinTile;
+  heads_count_kernel<K><<<(unsigned)ftiles, kThreads, 0, s>>>(sk, n, w.tile_heads);
+  if (ftiles <= kFusedHeadTiles) {
+    unique_finalize_kernel<K, true><<<(unsigned)ftiles, kThreads, 0, s>>>(
+        sk, sv, sb, n, flip, w.tile_heads, ftiles, uniq, inverse, seg_offsets, sorted_src,
+        num_unique);
+  } else {
+    heads_scan_kernel<<<1, 1024, 0, s>>>(w.tile_heads, ftiles, n, num_unique, seg_offsets);
+    unique_finalize_kernel<K, false><<<(unsigned)ftiles, kThreads, 0, s>>>(
+        sk, sv, sb, n, flip, w.tile_heads, ftiles, uniq, inverse, seg_offsets, sorted_src,
+        num_unique);
+  }
+  return hipGetLastError();
 }
 
 }  // namespace
@@ -508,85 +634,14 @@ hipError_t launch_unique(const void* ids, bool ids64, int64_t n, const int64_t* 
   }
   UniqueWs w = carve(workspace, n);
   const uint64_t flip = key_signed ? (1ull << 63) : 0ull;
-  const bool bags = offsets != nullptr && sorted_src != nullptr;
-
-  // a1: keys (and bags)
-  if (offsets) {
-    const int64_t num_bags = (int64_t)num_tables * batch;
-    const int64_t groups = (num_bags + 63) / 64;
-    // about 4096 waves, but no part shorter than one 64-occurrence stretch
-    int64_t parts = (4096 + groups - 1) / groups;
-    const int64_t stretches = (n / (groups > 0 ? groups : 1) + 63) / 64;
-    if (parts > stretches) parts = stretches;
-    if (parts < 1) parts = 1;
-    const int64_t blocks = (groups * parts + 3) / 4;
-    if (blocks > 0) {
-      if (ids64)
-        form_keys_bags_kernel<true><<<(unsigned)blocks, kThreads, 0, s>>>(
-            ids, n, offsets, batch, num_bags, row_base, modulus, flip, (int)parts, w.keys_a,
-            w.bags_a);
-      else
-        form_keys_bags_kernel<false><<<(unsigned)blocks, kThreads, 0, s>>>(
-            ids, n, offsets, batch, num_bags, row_base, modulus, flip, (int)parts, w.keys_a,
-            w.bags_a);
-    }
-  } else {
-    int64_t blocks = (n + kThreads - 1) / kThreads;
-    if (blocks > 8192) blocks = 8192;
-    if (ids64)
-      form_keys_flat_kernel<true><<<(unsigned)blocks, kThreads, 0, s>>>(ids, n, modulus, flip,
-                                                                        w.keys_a);
-    else
-      form_keys_flat_kernel<false><<<(unsigned)blocks, kThreads, 0, s>>>(ids, n, modulus, flip,
-                                                                         w.keys_a);
-  }
-
-  // a2: stable LSD radix sort of (key, occurrence[, bag]) over the live key bits
-  const int64_t ntiles = (n + kTile - 1) / kTile;
-  int nblocks = (int)(ntiles < kMaxBlocks ? ntiles : kMaxBlocks);
-  const int64_t tiles_per_block = (ntiles + nblocks - 1) / nblocks;
-  nblocks = (int)((ntiles + tiles_per_block - 1) / tiles_per_block);
-  const int64_t per_block = tiles_per_block * kTile;
-  const int passes = (key_bits + kMaxBits - 1) / kMaxBits;
-
-  uint64_t* kin = w.keys_a;
-  uint64_t* kout = w.keys_b;
-  // Values ping-pong so that the last pass lands in `perm` when the caller wants it.
-  uint32_t* vbuf[2];
-  if (perm) {
-    vbuf[0] = reinterpret_cast<uint32_t*>(perm);
-    vbuf[1] = w.vals_a;
-  } else {
-    vbuf[0] = w.vals_a;
-    vbuf[1] = w.vals_b;
-  }
-  const uint32_t* vin = nullptr;
-  uint32_t* bin = w.bags_a;
-  uint32_t* bout = w.bags_b;
-  int shift = 0;
-  for (int p = 0; p < passes; ++p) {
-    const int left = key_bits - shift;
-    const int nbits = (left + (passes - p) - 1) / (passes - p);   // spread bits evenly
-    uint32_t* vout = vbuf[(passes - 1 - p) & 1];
-    radix_pass<256>(p == 0, bags, kin, vin, bin, kout, vout, bout, n, shift, nbits, per_block,
-                    w.hist, w.totals, nblocks, s);
-    shift += nbits;
-    vin = vout;
-    std::swap(kin, kout);
-    std::swap(bin, bout);
-  }
-  const uint64_t* sk = kin;
-  const uint32_t* sv = vin;
-  const uint32_t* sb = bags ? bin : nullptr;
-
-  // finalize: heads, their scan, and the scatter of uniq / seg / inverse / sorted_src
-  const int64_t ftiles = (n + kFinTile - 1) / kFinTile;
-  heads_count_kernel<<<(unsigned)ftiles, kThreads, 0, s>>>(sk, n, w.tile_heads);
-  heads_scan_kernel<<<1, 1024, 0, s>>>(w.tile_heads, ftiles, n, num_unique, seg_offsets);
-  unique_finalize_kernel<<<(unsigned)ftiles, kThreads, 0, s>>>(sk, sv, sb, n, flip, w.tile_heads,
-                                                               uniq, inverse, seg_offsets,
-                                                               sorted_src);
-  return hipGetLastError();
+  // 32-bit keys whenever the live key range fits (a quarter less sort traffic)
+  if (!key_signed && key_bits <= 32)
+    return unique_impl<uint32_t>(ids, ids64, n, offsets, batch, num_tables, row_base, modulus,
+                                 key_bits, flip, uniq, inverse, num_unique, perm, seg_offsets,
+                                 sorted_src, w, s);
+  return unique_impl<uint64_t>(ids, ids64, n, offsets, batch, num_tables, row_base, modulus,
+                               key_bits, flip, uniq, inverse, num_unique, perm, seg_offsets,
+                               sorted_src, w, s);
 }
 
 }  // namespace ctr
