@@ -89,10 +89,12 @@ const char* ctr_last_error(void);
  *                    (nullable)
  *   seg_offsets[u]   first sorted position of uniq[u]; seg_offsets[U] = n      int32 [n+1]
  *                    (nullable)
- *   sorted_src[2p], sorted_src[2p+1]  (u, bag) of the occurrence at sorted position p,
- *                    int32 pairs [n] (nullable; 8-byte aligned).  The bag is t*batch + b
- *                    when offsets are given, else the occurrence index itself.  This is the
- *                    input ctr_embbag_bwd needs, produced here at no extra pass.
+ *   sorted_src[4p .. 4p+3]  (u, bag, key low word, key high word) of the occurrence at
+ *                    sorted position p: int32 quadruples [n] (nullable; 16-byte aligned).
+ *                    The bag is t*batch + b when offsets are given, else the occurrence
+ *                    index itself; the key is uniq[u] as int64 (little-endian words).  This
+ *                    is the input the backward needs, written by the same pass, so that it
+ *                    reaches the gradient row and the table row of a position in one read.
  * Key range: with row_base the keys must lie in [0, total_rows); with only a modulus in
  * [0, key_modulus); otherwise any int64.  The sort covers only the live key bits.
  * n == 0 is legal: U = 0, seg_offsets[0] = 0.
@@ -135,8 +137,9 @@ int32_t ctr_embbag_fwd(const void* table, int32_t dtype, int64_t total_rows, int
  *   row_grads[u, c] = sum over occurrences i with inverse[i] == u of
  *                     grad[b(i)*grad_stride_b + t(i)*grad_stride_t + c]
  * where bag (t(i), b(i)) holds occurrence i.  The grouping comes from ctr_unique_ids for the
- * same occurrences: either its sorted_src pairs (preferred: read in order), or perm and
- * inverse (then the bags are expanded from offsets and gathered in sorted order here).
+ * same occurrences: either its sorted_src quadruples (preferred: read in order; only u and
+ * the bag are used here), or perm and inverse (then the bags are expanded from offsets and
+ * gathered in sorted order here).
  * The sum runs in sorted order as a fixed-shape tree over chunks (deterministic, no
  * atomics).  row_grads: fp32 [nnz, dim]; rows u >= U untouched.  Workspace: two-call query.
  */
@@ -152,7 +155,8 @@ int32_t ctr_embbag_bwd(const float* grad, int64_t grad_stride_b, int64_t grad_st
  *   table[uniq[u], :] = round(table[uniq[u], :] - lr * g[u, :])
  * with exactly the arithmetic of ctr_sparse_sgd (so the table ends bit-identical to the
  * two-call path), without writing g to memory and reading it back.  row_grads is optional
- * (NULL: gradients are not kept).  Grouping from ctr_unique_ids' sorted_src and uniq.
+ * (NULL: gradients are not kept).  Grouping and table rows from ctr_unique_ids' sorted_src
+ * (u, bag, key); uniq serves the rows of segments that span several chunks.
  * dtype/total_rows/dim describe the table as in ctr_sparse_sgd; dim <= 1024.  Workspace:
  * two-call query, same size as ctr_embbag_bwd.
  */

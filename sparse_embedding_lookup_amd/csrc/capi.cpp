@@ -101,8 +101,8 @@ int32_t ctr_unique_ids(const void* ids, int32_t id_type, int64_t n, const int64_
   if (!num_unique) return fail(CTR_ERR_INVALID_ARGUMENT, "num_unique is NULL");
   if (n > 0 && (!ids || !uniq || !inverse))
     return fail(CTR_ERR_INVALID_ARGUMENT, "ids, uniq and inverse are required");
-  if (sorted_src && (reinterpret_cast<uintptr_t>(sorted_src) & 7u))
-    return fail(CTR_ERR_UNSUPPORTED, "sorted_src is not 8-byte aligned");
+  if (sorted_src && (reinterpret_cast<uintptr_t>(sorted_src) & 15u))
+    return fail(CTR_ERR_UNSUPPORTED, "sorted_src is not 16-byte aligned");
   int bits;
   bool is_signed = false;
   if (row_base) {
@@ -117,7 +117,7 @@ int32_t ctr_unique_ids(const void* ids, int32_t id_type, int64_t n, const int64_
   return hip_status(ctr::launch_unique(ids, id_type == CTR_I64, n, offsets, batch, num_tables,
                                        row_base, key_modulus, bits, is_signed, uniq, inverse,
                                        num_unique, perm, seg_offsets,
-                                       reinterpret_cast<int2*>(sorted_src), workspace,
+                                       reinterpret_cast<int4*>(sorted_src), workspace,
                                        (hipStream_t)stream),
                     "ctr_unique_ids");
 }
@@ -193,8 +193,8 @@ int32_t ctr_embbag_bwd(const float* grad, int64_t grad_stride_b, int64_t grad_st
     return fail(CTR_ERR_INVALID_ARGUMENT, "grad and row_grads are required");
   if (nnz > 0 && !sorted_src && (!perm || !inverse))
     return fail(CTR_ERR_INVALID_ARGUMENT, "either sorted_src or perm and inverse are required");
-  if (sorted_src && (reinterpret_cast<uintptr_t>(sorted_src) & 7u))
-    return fail(CTR_ERR_UNSUPPORTED, "sorted_src is not 8-byte aligned");
+  if (sorted_src && (reinterpret_cast<uintptr_t>(sorted_src) & 15u))
+    return fail(CTR_ERR_UNSUPPORTED, "sorted_src is not 16-byte aligned");
   if (grad_stride_b < 0 || grad_stride_t < 0)
     return fail(CTR_ERR_INVALID_ARGUMENT, "negative gradient stride");
   if ((grad && !aligned16(grad)) || (row_grads && !aligned16(row_grads)) || grad_stride_b % 4 ||
@@ -203,7 +203,7 @@ int32_t ctr_embbag_bwd(const float* grad, int64_t grad_stride_b, int64_t grad_st
   if (!aligned16(workspace)) return fail(CTR_ERR_UNSUPPORTED, "workspace is not 16-byte aligned");
   return hip_status(ctr::launch_embbag_bwd(grad, grad_stride_b, grad_stride_t, offsets, batch,
                                            num_tables, dim, nnz, perm, inverse,
-                                           reinterpret_cast<const int2*>(sorted_src), num_unique,
+                                           reinterpret_cast<const int4*>(sorted_src), num_unique,
                                            row_grads, nullptr, 0, 0, nullptr, 0.f, workspace,
                                            (hipStream_t)stream),
                     "ctr_embbag_bwd");
@@ -242,12 +242,12 @@ int32_t ctr_embbag_bwd_sgd(const float* grad, int64_t grad_stride_b, int64_t gra
   if ((grad && !aligned16(grad)) || (row_grads && !aligned16(row_grads)) || grad_stride_b % 4 ||
       grad_stride_t % 4)
     return fail(CTR_ERR_UNSUPPORTED, "grad/row_grads must be 16-byte aligned, strides multiple of 4");
-  if (reinterpret_cast<uintptr_t>(sorted_src) & 7u)
-    return fail(CTR_ERR_UNSUPPORTED, "sorted_src is not 8-byte aligned");
+  if (reinterpret_cast<uintptr_t>(sorted_src) & 15u)
+    return fail(CTR_ERR_UNSUPPORTED, "sorted_src is not 16-byte aligned");
   if (!aligned16(workspace)) return fail(CTR_ERR_UNSUPPORTED, "workspace is not 16-byte aligned");
   return hip_status(ctr::launch_embbag_bwd(grad, grad_stride_b, grad_stride_t, offsets, batch,
                                            num_tables, dim, nnz, nullptr, nullptr,
-                                           reinterpret_cast<const int2*>(sorted_src), num_unique,
+                                           reinterpret_cast<const int4*>(sorted_src), num_unique,
                                            row_grads, table, dtype == CTR_BF16 ? 2 : 1,
                                            total_rows, uniq, lr, workspace, (hipStream_t)stream),
                     "ctr_embbag_bwd_sgd");

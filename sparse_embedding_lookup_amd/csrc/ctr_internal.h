@@ -84,7 +84,7 @@ hipError_t launch_unique(const void* ids, bool ids64, int64_t n, const int64_t* 
                          int64_t batch, int32_t num_tables, const int64_t* row_base,
                          int64_t modulus, int key_bits, bool key_signed, int64_t* uniq,
                          int32_t* inverse, int32_t* num_unique, int32_t* perm,
-                         int32_t* seg_offsets, int2* sorted_src, void* workspace,
+                         int32_t* seg_offsets, int4* sorted_src, void* workspace,
                          hipStream_t s);
 
 // embbag.hip
@@ -108,7 +108,7 @@ hipError_t launch_validate_csr(const void* idx, bool idx64, int64_t nnz, const i
 size_t embbag_bwd_workspace_bytes(int64_t nnz, int dim);
 hipError_t launch_embbag_bwd(const float* grad, int64_t sb, int64_t st, const int64_t* offsets,
                              int64_t batch, int32_t num_tables, int dim, int64_t nnz,
-                             const int32_t* perm, const int32_t* inverse, const int2* sorted_src,
+                             const int32_t* perm, const int32_t* inverse, const int4* sorted_src,
                              const int32_t* num_unique, float* row_grads, void* table,
                              int sgd_mode, int64_t total_rows, const int64_t* uniq, float lr,
                              void* workspace, hipStream_t s);

@@ -2,26 +2,28 @@
 // the batch's distinct rows ("How TensorNet Supercharges Sparse Feature Training on
 // TensorFlow", "Synchronous Architecture": only rows present in the batch get anything).
 //
-// Inputs come from the unique step: perm (sorted position -> occurrence) and inverse
-// (occurrence -> distinct-row index u).  Three steps, all deterministic, no atomics:
-//   1. bag_of[i]   bag of every occurrence (a wave expands 64 bags, lanes binary-search the
-//                  64 bag ends with shuffles, stores are coalesced)
-//   2. src[p]      (u, bag) of sorted position p
-//   3. a reduce-by-key over the sorted sequence in fixed chunks, so that a row hit a million
-//      times costs the same as a million rows hit once.  A workgroup owns a chunk of
-//      S*kPerSlot positions; each G-lane slot sums kPerSlot consecutive positions serially
-//      (G lanes x 16 B per row) and writes finished segments straight to row_grads; the
-//      pieces of segments that cross slot edges are joined in LDS; pieces that cross the
-//      chunk edges go out as at most two carries per chunk.  The carries (key, row) form a
-//      sequence of the same kind, reduced by the same kernel, until one chunk is left:
-//      a tree of fixed shape whose depth is ceil(log_chunk(n)).
+// Input: the unique step's (u, bag, table row) per sorted position, or perm (sorted
+// position -> occurrence) and inverse (occurrence -> u), from which two small kernels build
+// (u, bag) per sorted position first (a wave expands 64 bags by a shuffle binary search
+// over their ends; then one gather in sorted order).  Then a deterministic reduce-by-key
+// over the sorted sequence in fixed chunks, so that a row hit a million times costs the
+// same as a million rows hit once.  A workgroup owns a chunk of S*kPerSlot positions; each
+// G-lane slot (G lanes x 16 B per row) sums kPerSlot consecutive positions, with every
+// gradient row and every table row it needs requested before it adds anything, and writes
+// the segments it completes straight out (row_grads and/or the SGD update); the pieces of
+// segments that cross slot edges are joined in LDS; pieces that cross the chunk edges go
+// out as at most two carries per chunk.  The carries (key, row) form a sequence of the same
+// kind, reduced by the same kernel, until one chunk is left: a tree of fixed shape whose
+// depth is ceil(log_chunk(n)).  No atomics anywhere.
+#include <type_traits>
+
 #include "ctr_internal.h"
 
 namespace ctr {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kPerSlot = 16;     // positions summed serially by one slot
+constexpr int kPerSlot = 8;      // positions summed by one slot (more slots, fewer registers)
 
 __global__ __launch_bounds__(kThreads) void bag_of_kernel(const int64_t* __restrict__ offsets,
                                                           int64_t num_bags, int64_t nnz,
@@ -52,17 +54,17 @@ __global__ __launch_bounds__(kThreads) void bag_of_kernel(const int64_t* __restr
 __global__ __launch_bounds__(kThreads) void seg_src_kernel(const int32_t* __restrict__ perm,
                                                            const int32_t* __restrict__ inverse,
                                                            const int32_t* __restrict__ bag_of,
-                                                           int64_t n, int2* __restrict__ src) {
+                                                           int64_t n, int4* __restrict__ src) {
   const int64_t p = (int64_t)blockIdx.x * kThreads + threadIdx.x;
   if (p >= n) return;
   const int32_t i = perm[p];
-  int2 r = make_int2(-1, 0);
-  if (i >= 0 && (int64_t)i < n) r = make_int2(inverse[i], bag_of[i]);
+  int4 r = make_int4(-1, 0, -1, -1);                       // the key is not needed here
+  if (i >= 0 && (int64_t)i < n) r = make_int4(inverse[i], bag_of[i], -1, -1);
   src[p] = r;
 }
 
 struct L0Source {
-  const int2* src;
+  const int4* src;
   const float* grad;
   int64_t sb, st, batch, num_bags;
   __device__ __forceinline__ int32_t key(int64_t p) const { return src[p].x; }
@@ -124,6 +126,172 @@ struct SegSmem {
   int32_t wg_last_key;
 };
 
+// Table-row part of one lane (4 columns) and its update W <- W - lr * g: one fused
+// multiply-add in fp32, then a plain store (fp32) or nearest-even to bf16.
+template <int MODE>
+using WVec = typename std::conditional<MODE == 2, uint2, float4>::type;
+
+template <int MODE>
+__device__ __forceinline__ WVec<MODE> load_wvec(const SgdTarget& sgd, int64_t key, int c,
+                                                bool ok) {
+  const char* wrow = sgd.table + key * sgd.row_bytes;
+  if constexpr (MODE == 2)
+    return ok ? *reinterpret_cast<const uint2*>(wrow + (int64_t)c * 2) : make_uint2(0u, 0u);
+  else
+    return ok ? *reinterpret_cast<const float4*>(wrow + (int64_t)c * 4)
+              : make_float4(0.f, 0.f, 0.f, 0.f);
+}
+
+template <int MODE>
+__device__ __forceinline__ void store_updated(const SgdTarget& sgd, int64_t key, int c,
+                                              const float4& g, const WVec<MODE>& x) {
+  char* wrow = sgd.table + key * sgd.row_bytes;
+  if constexpr (MODE == 1) {
+    *reinterpret_cast<float4*>(wrow + (int64_t)c * 4) =
+        make_float4(__builtin_fmaf(-sgd.lr, g.x, x.x), __builtin_fmaf(-sgd.lr, g.y, x.y),
+                    __builtin_fmaf(-sgd.lr, g.z, x.z), __builtin_fmaf(-sgd.lr, g.w, x.w));
+  } else if constexpr (MODE == 2) {
+    const float n0 = __builtin_fmaf(-sgd.lr, g.x, bf16_lo(x.x));
+    const float n1 = __builtin_fmaf(-sgd.lr, g.y, bf16_hi(x.x));
+    const float n2 = __builtin_fmaf(-sgd.lr, g.z, bf16_lo(x.y));
+    const float n3 = __builtin_fmaf(-sgd.lr, g.w, bf16_hi(x.y));
+    *reinterpret_cast<uint2*>(wrow + (int64_t)c * 2) =
+        make_uint2(f32_to_bf16_bits(n0) | (f32_to_bf16_bits(n1) << 16),
+                   f32_to_bf16_bits(n2) | (f32_to_bf16_bits(n3) << 16));
+  }
+}
+
+// The table row a slot holds for the piece it may finish after the chunk's join.
+template <int MODE>
+struct PendingRow {
+  int64_t key = -1;
+  WVec<MODE> w;
+};
+
+// Sum the slot's kPerSlot sorted positions when one 16-byte vector per lane covers a row
+// (d <= 4G).  Each sorted position carries (u, bag, table row), so the slot issues every
+// memory access it needs in two dependent rounds: its entries, then all gradient rows
+// together with the table rows of the segments it completes (and of its last piece, which
+// it may complete after the chunk's join).  A position ends a piece where the next key
+// differs; a piece whose key equals the key just before the slot began earlier (sorted
+// keys), and one whose key equals the key just after continues later: those two go to LDS
+// for the join, every other piece is complete and is written out (and applied) here.
+template <int G, int MODE>
+__device__ __forceinline__ void slot_prefetched(const L0Source& S, int64_t q0, int64_t q1,
+                                                int64_t n, int dim, int64_t capacity,
+                                                float* __restrict__ row_grads,
+                                                const SgdTarget& sgd, SegSmem<G, 1>& sm, int slot,
+                                                int lane, int32_t& fkey, int32_t& fcont,
+                                                int32_t& lkey, PendingRow<MODE>& pend) {
+  constexpr int kRegs = (kPerSlot + G - 1) / G;
+  const int lane0 = (threadIdx.x & 63) & ~(G - 1);
+  const int len = (int)(q1 - q0);
+  const int c = lane * 4;
+  const bool col_ok = c < dim;
+
+  // (u, bag, row) of position e = r*G + lane in register r
+  int32_t ekey[kRegs];
+  int32_t ebag[kRegs];
+  int64_t erow[kRegs];
+#pragma unroll
+  for (int r = 0; r < kRegs; ++r) {
+    const int e = r * G + lane;
+    ekey[r] = -1;
+    ebag[r] = 0;
+    erow[r] = -1;
+    if (e < kPerSlot && e < len) {
+      const int4 sr = S.src[q0 + e];
+      ekey[r] = sr.x;
+      ebag[r] = sr.y;
+      erow[r] = (int64_t)(((uint64_t)(uint32_t)sr.w << 32) | (uint32_t)sr.z);
+    }
+  }
+  const int32_t kb = key_before<true>(S, q0);
+  const int32_t ka = key_after<true>(S, q1, n);
+
+  // all gradient rows of the slot
+  int32_t kk[kPerSlot];
+  float4 rv[kPerSlot];
+#pragma unroll
+  for (int e = 0; e < kPerSlot; ++e) {
+    kk[e] = __shfl(ekey[e / G], lane0 + (e % G), 64);
+    uint32_t bag = (uint32_t)__shfl(ebag[e / G], lane0 + (e % G), 64);
+    if ((int64_t)bag >= S.num_bags) bag = 0;
+    const uint32_t t = bag / (uint32_t)S.batch, b = bag - t * (uint32_t)S.batch;
+    const float* rp = S.grad + (int64_t)b * S.sb + (int64_t)t * S.st;
+    rv[e] = (e < len && col_ok && kk[e] != -1) ? *reinterpret_cast<const float4*>(rp + c)
+                                               : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+
+  // table rows of the segments completed inside the slot, and of the last piece
+  int64_t rk[kRegs];
+  WVec<MODE> w[kPerSlot];
+  if constexpr (MODE != 0) {
+#pragma unroll
+    for (int r = 0; r < kRegs; ++r) {
+      const int e = r * G + lane;
+      const int32_t own = ekey[r];
+      // key of position e + 1: same register one lane up, or register r + 1 of lane 0
+      const int32_t up = __shfl(ekey[r], lane0 + ((lane + 1) & (G - 1)), 64);
+      const int32_t wrap = (r + 1 < kRegs) ? __shfl(ekey[r + 1 < kRegs ? r + 1 : r], lane0, 64)
+                                           : -1;
+      const int32_t nx = (e + 1 < len) ? ((lane + 1 < G) ? up : wrap) : ka;
+      const bool emit = e < kPerSlot && e < len && own != kb && nx != own && own >= 0 &&
+                        (int64_t)own < capacity;
+      const bool last = e == len - 1 && own == ka && own != kb && own >= 0 &&
+                        (int64_t)own < capacity;
+      const int64_t key = erow[r];
+      rk[r] = ((emit || last) && key >= 0 && key < sgd.total_rows) ? key : -1;
+    }
+#pragma unroll
+    for (int e = 0; e < kPerSlot; ++e) {
+      const int64_t key = __shfl(rk[e / G], lane0 + (e % G), 64);
+      w[e] = load_wvec<MODE>(sgd, key, c, key >= 0 && col_ok);
+    }
+  }
+
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+  for (int e = 0; e < kPerSlot; ++e) {
+    if (e < len) {
+      acc.x += rv[e].x;
+      acc.y += rv[e].y;
+      acc.z += rv[e].z;
+      acc.w += rv[e].w;
+      const int32_t k = kk[e];
+      const int32_t nx = (e + 1 < len) ? kk[e + 1 < kPerSlot ? e + 1 : e] : ka;
+      if (nx != k) {                           // the piece ends at e
+        if (k == kb) {                         // ... and began before the slot
+          fkey = k;
+          fcont = 0;
+          *reinterpret_cast<float4*>(&sm.first_row[slot][c]) = acc;
+        } else if (k >= 0 && (int64_t)k < capacity) {
+          if (row_grads && col_ok)
+            *reinterpret_cast<float4*>(row_grads + (int64_t)k * dim + c) = acc;
+          if constexpr (MODE != 0) {
+            const int64_t key = __shfl(rk[e / G], lane0 + (e % G), 64);
+            if (key >= 0 && col_ok) store_updated<MODE>(sgd, key, c, acc, w[e]);
+          }
+        }
+        acc = make_float4(0.f, 0.f, 0.f, 0.f);
+      } else if (e == len - 1) {               // still open at the slot's end: continues
+        if (k == kb) {
+          fkey = k;
+          fcont = 1;
+          *reinterpret_cast<float4*>(&sm.first_row[slot][c]) = acc;
+        } else {
+          lkey = k;
+          *reinterpret_cast<float4*>(&sm.last_row[slot][c]) = acc;
+          if constexpr (MODE != 0) {
+            pend.key = __shfl(rk[e / G], lane0 + (e % G), 64);
+            pend.w = w[e];
+          }
+        }
+      }
+    }
+  }
+}
+
 // One reduce-by-key level.  L0: entries are sorted positions of the occurrences (keys from
 // src, rows gathered from grad); otherwise entries are carries (keys may be -1 = empty).
 template <bool L0, int G, int VPL, int MODE, typename Src>
@@ -183,7 +351,12 @@ __global__ __launch_bounds__(kThreads) void segreduce_kernel(
   };
 
   int32_t fkey = -1, fcont = 0, lkey = -1;
-  if (q0 < n) {
+  PendingRow<MODE> pend;
+  if constexpr (L0 && VPL == 1) {
+    if (q0 < n)
+      slot_prefetched<G, MODE>(S, q0, q1, n, dim, capacity, row_grads, sgd, sm, slot, lane,
+                               fkey, fcont, lkey, pend);
+  } else if (q0 < n) {
     // Prefetch the slot's entries cooperatively: entry e is loaded by lane e % G of the slot
     // into register e / G, then broadcast with shuffles.
     constexpr int kRegs = (kPerSlot + G - 1) / G;
@@ -198,7 +371,7 @@ __global__ __launch_bounds__(kThreads) void segreduce_kernel(
       ebag[r] = 0;
       if (e < kPerSlot && p < q1) {
         if constexpr (L0) {
-          const int2 sr = S.src[p];
+          const int4 sr = S.src[p];
           ekey[r] = sr.x;
           ebag[r] = sr.y;
         } else {
@@ -344,7 +517,18 @@ __global__ __launch_bounds__(kThreads) void segreduce_kernel(
       acc.v[a][0] = x.x; acc.v[a][1] = x.y; acc.v[a][2] = x.z; acc.v[a][3] = x.w;
     }
     if (walk(u, slot + 1, acc)) {
-      emit_complete(u, acc);
+      if constexpr (L0 && VPL == 1) {
+        // the row was read before the join
+        if (u >= 0 && (int64_t)u < capacity) {
+          const int c = col(0);
+          const float4 g = make_float4(acc.v[0][0], acc.v[0][1], acc.v[0][2], acc.v[0][3]);
+          if (row_grads && c < dim) *reinterpret_cast<float4*>(row_grads + (int64_t)u * dim + c) = g;
+          if constexpr (MODE != 0)
+            if (pend.key >= 0 && c < dim) store_updated<MODE>(sgd, pend.key, c, g, pend.w);
+        }
+      } else {
+        emit_complete(u, acc);
+      }
     } else {
       write_row(out_rows + (carry_base + 1) * dim, acc);
       if (lane == 0) sm.wg_last_key = u;
@@ -362,7 +546,7 @@ inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct BwdWs {
   int32_t* bag_of;
-  int2* src;
+  int4* src;
   int32_t* ckeys[2];
   float* crows[2];
   size_t bytes;
@@ -385,7 +569,7 @@ BwdWs carve(void* base, int64_t n, int dim) {
   const int64_t chunk = chunk_positions(dim);
   const int64_t c1 = 2 * ((n + chunk - 1) / chunk);   // carries out of level 0 (largest)
   w.bag_of = reinterpret_cast<int32_t*>(take(sizeof(int32_t) * (size_t)n));
-  w.src = reinterpret_cast<int2*>(take(sizeof(int2) * (size_t)n));
+  w.src = reinterpret_cast<int4*>(take(sizeof(int4) * (size_t)n));
   for (int k = 0; k < 2; ++k) {
     w.ckeys[k] = reinterpret_cast<int32_t*>(take(sizeof(int32_t) * (size_t)(c1 + 2)));
     w.crows[k] = reinterpret_cast<float*>(take(sizeof(float) * (size_t)(c1 + 2) * dim));
@@ -441,7 +625,7 @@ static void segreduce_levels(const L0Source& s0, int64_t nnz, int dim, float* ro
 
 hipError_t launch_embbag_bwd(const float* grad, int64_t sb, int64_t st, const int64_t* offsets,
                              int64_t batch, int32_t num_tables, int dim, int64_t nnz,
-                             const int32_t* perm, const int32_t* inverse, const int2* sorted_src,
+                             const int32_t* perm, const int32_t* inverse, const int4* sorted_src,
                              const int32_t* num_unique, float* row_grads, void* table,
                              int sgd_mode, int64_t total_rows, const int64_t* uniq, float lr,
                              void* workspace, hipStream_t s) {
@@ -450,7 +634,7 @@ hipError_t launch_embbag_bwd(const float* grad, int64_t sb, int64_t st, const in
   BwdWs w = carve(workspace, nnz, dim);
   const int64_t num_bags = (int64_t)num_tables * batch;
 
-  const int2* src = sorted_src;
+  const int4* src = sorted_src;
   if (!src) {
     // (u, bag) per sorted position from perm and inverse: expand the bags, then gather.
     const int64_t waves = (num_bags + 63) / 64;

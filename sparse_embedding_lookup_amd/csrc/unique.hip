@@ -380,15 +380,15 @@ __global__ __launch_bounds__(1024) void heads_scan_kernel(uint32_t* __restrict__
   }
 }
 
-// sorted_src[p] = (distinct-row index of position p, bag of its occurrence); without bags
-// the occurrence is its own bag.  FUSED: the block sums the head counts of the tiles before
+// sorted_src[p] = (distinct-row index of position p, bag of its occurrence, key as two
+// words); without bags the occurrence is its own bag.  FUSED: the block sums the head counts of the tiles before
 // it itself (few tiles), and the last block publishes U.
 template <typename K, bool FUSED>
 __global__ __launch_bounds__(kThreads) void unique_finalize_kernel(
     const K* __restrict__ sk, const uint32_t* __restrict__ sv, const uint32_t* __restrict__ sbag,
     int64_t n, uint64_t flip, const uint32_t* __restrict__ tile_heads, int64_t ntiles,
     int64_t* __restrict__ uniq, int32_t* __restrict__ inverse, int32_t* __restrict__ seg_offsets,
-    int2* __restrict__ sorted_src, int32_t* __restrict__ num_unique) {
+    int4* __restrict__ sorted_src, int32_t* __restrict__ num_unique) {
   __shared__ uint32_t wsum[4];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const uint64_t le = (lane == 63) ? ~0ull : ((2ull << lane) - 1ull);
@@ -434,13 +434,16 @@ __global__ __launch_bounds__(kThreads) void unique_finalize_kernel(
     __syncthreads();
     if (p < n) {
       const uint32_t r = before + (uint32_t)__popcll(m & le) - 1u;   // heads <= p, minus one
+      const uint64_t key = (uint64_t)k ^ flip;
       if (h) {
-        uniq[r] = (int64_t)((uint64_t)k ^ flip);
+        uniq[r] = (int64_t)key;
         if (seg_offsets) seg_offsets[r] = (int32_t)p;
       }
       const uint32_t occ = sv[p];
       if (occ < (uint64_t)n) inverse[occ] = (int32_t)r;
-      if (sorted_src) sorted_src[p] = make_int2((int32_t)r, (int32_t)(sbag ? sbag[p] : occ));
+      if (sorted_src)
+        sorted_src[p] = make_int4((int32_t)r, (int32_t)(sbag ? sbag[p] : occ), (int32_t)key,
+                                  (int32_t)(key >> 32));
     }
     base += total;
   }
@@ -552,7 +555,7 @@ hipError_t unique_impl(const void* ids, bool ids64, int64_t n, const int64_t* of
                        int64_t batch, int32_t num_tables, const int64_t* row_base,
                        int64_t modulus, int key_bits, uint64_t flip, int64_t* uniq,
                        int32_t* inverse, int32_t* num_unique, int32_t* perm,
-                       int32_t* seg_offsets, int2* sorted_src, UniqueWs& w, hipStream_t s) {
+                       int32_t* seg_offsets, int4* sorted_src, UniqueWs& w, hipStream_t s) {
   const bool bags = offsets != nullptr && sorted_src != nullptr;
   K* keys_a = static_cast<K*>(w.keys_a);
   K* keys_b = static_cast<K*>(w.keys_b);
@@ -626,7 +629,7 @@ hipError_t launch_unique(const void* ids, bool ids64, int64_t n, const int64_t* 
                          int64_t batch, int32_t num_tables, const int64_t* row_base,
                          int64_t modulus, int key_bits, bool key_signed, int64_t* uniq,
                          int32_t* inverse, int32_t* num_unique, int32_t* perm,
-                         int32_t* seg_offsets, int2* sorted_src, void* workspace,
+                         int32_t* seg_offsets, int4* sorted_src, void* workspace,
                          hipStream_t s) {
   if (n == 0) {
     unique_empty_kernel<<<1, 64, 0, s>>>(num_unique, seg_offsets);

@@ -166,7 +166,8 @@ def ctr_unique_ids(ids: torch.Tensor, *, offsets: Optional[torch.Tensor] = None,
     """Returns (uniq int64[n], inverse int32[n], num_unique int32[1], perm, seg_offsets);
     only the first num_unique entries of uniq (and num_unique+1 of seg_offsets) are set.
     ``out`` may supply those five tensors (perm / seg_offsets may be None); ``sorted_src``
-    (int32 [n, 2]) receives the (distinct-row index, bag) pair of every sorted position."""
+    (int32 [n, 4], 16-byte aligned) receives (distinct-row index, bag, key low word, key high
+    word) for every sorted position."""
     n = ids.numel()
     dev = ids.device
     if out is not None:

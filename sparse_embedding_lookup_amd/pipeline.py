@@ -77,7 +77,7 @@ class FrontEnd:
         self.num_unique = torch.zeros(1, dtype=torch.int32, device=dv)
         self.perm = torch.empty(max(n, 1), dtype=torch.int32, device=dv)
         self.seg = torch.empty(n + 1, dtype=torch.int32, device=dv)
-        self.sorted_src = torch.empty((max(n, 1), 2), dtype=torch.int32, device=dv)
+        self.sorted_src = torch.empty((max(n, 1), 4), dtype=torch.int32, device=dv)
         self._unique_out = (self.uniq, self.inverse, self.num_unique, self.perm, self.seg)
         self.side = None
 

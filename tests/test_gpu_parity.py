@@ -119,12 +119,12 @@ def test_unique_matches_oracle(name):
 @pytest.mark.parametrize("name", ["tiny_tables", "small_tables", "tensornet_mod", "all_equal",
                                   "raw_signed"])
 def test_unique_sorted_src(name):
-    """(u, bag) per sorted position: u = inverse[perm[p]], bag = bag holding perm[p] (or the
-    occurrence itself without bags)."""
+    """(u, bag, key) per sorted position: u = inverse[perm[p]], bag = bag holding perm[p] (or
+    the occurrence itself without bags), key = uniq[u] as two int32 words."""
     ids, kw = UNIQUE_CASES[name]
     say("unique sorted_src", name)
     n = ids.size
-    src = torch.empty((n, 2), dtype=torch.int32, device=DEV)
+    src = torch.empty((n, 4), dtype=torch.int32, device=DEV)
     if "offsets" in kw:
         rb = np.zeros(len(kw["rows"]) + 1, dtype=np.int64)
         rb[1:] = np.cumsum(kw["rows"])
@@ -142,6 +142,8 @@ def test_unique_sorted_src(name):
     got = host(src)
     np.testing.assert_array_equal(got[:, 0], oi[op])
     np.testing.assert_array_equal(got[:, 1], bag_of[op])
+    np.testing.assert_array_equal(np.ascontiguousarray(got[:, 2:]).view(np.int64)[:, 0],
+                                  ou[oi[op]])
 
 
 def test_unique_empty():
@@ -328,11 +330,13 @@ def test_embbag_bwd_matches_oracle(name):
     got = host(rg)[:U]
     want, mag = orc.embbag_bwd(dZ[:, 1:, :].astype(np.float64), off, B, T, inv, U)
     assert_close(got, want, mag, RTOL_F32, "embbag_bwd " + name)
-    # the same through (u, bag) pairs per sorted position, as the unique step emits them
+    # the same through (u, bag, key) entries per sorted position, as the unique step emits them
     bag_of = np.searchsorted(off, np.arange(len(ids)), side="right") - 1
-    pairs = np.stack([inv[perm], bag_of[perm]], axis=1).astype(np.int32)
+    quads = np.zeros((len(ids), 4), dtype=np.int32)
+    quads[:, 0], quads[:, 1] = inv[perm], bag_of[perm]
+    quads[:, 2:] = uniq[inv[perm]].astype(np.int64).view(np.int32).reshape(-1, 2)
     rg2 = ctr.ctr_embbag_bwd(g_dev[:, 1:, :], (T + 1) * dim, dim, dev(off), B, T, dim, None, None,
-                             dev(np.array([U], np.int32)), sorted_src=dev(pairs), nnz=len(ids))
+                             dev(np.array([U], np.int32)), sorted_src=dev(quads), nnz=len(ids))
     np.testing.assert_array_equal(host(rg2)[:U], got)
 
 
