@@ -12,7 +12,18 @@ algorithmic bytes, interaction samples/s, the roofline of the dominant kernel (t
 HIP events on its stream inside the timed region) and the CPU oracle timed on a bounded
 sample of the same workload.
 
+Schedule (default "pipelined"): training consumes a stream of batches, and the ID dedup of
+batch k+1 needs only that batch's IDs, so it runs on a second stream during step k (forked
+right after the dominant kernel, which thus runs alone) into a second set of output
+buffers; each timed step still launches every call of the path once.
+The next batch's unique (side stream) and the main-stream stages after the dominant kernel
+replay from captured graphs to take the host's launch cost off the step; the stages up to
+the dominant kernel stay eager, so that HIP events on its stream time it in place.  "serial"
+dedups each batch inside its own step (eager); the pipelined run also reports that
+schedule's ms per step.
+
     python bench.py [--config small|tiny|criteo|tensornet|large] [--steps K] [--warmup W]
+                    [--schedule pipelined|serial] [--graph]
 """
 from __future__ import annotations
 
@@ -167,6 +178,9 @@ def main():
                     help="run one device copy of MB MiB first (scale for HBM byte counters)")
     ap.add_argument("--graph", action="store_true",
                     help="replay captured HIP graph segments instead of launching from the host")
+    ap.add_argument("--schedule", default="pipelined", choices=["pipelined", "serial"],
+                    help="pipelined: batch k+1's ID dedup runs during step k (double-buffered "
+                         "outputs); serial: every step dedups its own batch first")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -181,7 +195,8 @@ def main():
     print("[bench] generating workload %s" % args.config, file=sys.stderr, flush=True)
     w = workloads.make(args.config)
     print("[bench] nnz=%d, building device state" % w.nnz, file=sys.stderr, flush=True)
-    fe = FrontEnd(w, "cuda")
+    pipelined = args.schedule == "pipelined" and not args.graph
+    fe = FrontEnd(w, "cuda", pipelined=pipelined)
     st = fe.stages()
     torch.cuda.synchronize()
     if args.copy_calibration:
@@ -199,6 +214,7 @@ def main():
         fe.step()
     torch.cuda.synchronize()
     U = int(fe.num_unique.cpu()[0])
+
     K = args.steps
 
     # Per-stage durations (diagnostic, before the timed region): each stage alone, as a
@@ -221,6 +237,15 @@ def main():
     stage_ms = {n: sum(e0.elapsed_time(e1) for e0, e1 in evs[n]) / K for n in names}
     byts = stage_bytes(w, U)
     dominant = max((s for s in stage_ms if s in SINGLE_KERNEL), key=lambda s: stage_ms[s])
+    if pipelined:
+        # the next batch's unique and the stages after the dominant kernel replay from captured
+        # graphs (host launch cost); the stages up to the dominant one stay eager so that HIP
+        # events on the main stream bracket the dominant kernel itself
+        fe.capture_pipelined_parts(fork_after=dominant)
+        fe.pipeline_start()
+        for _ in range(args.warmup):
+            fe.step_pipelined(fork_after=dominant)
+        torch.cuda.synchronize()
 
     # Timed region: K whole steps.  Graph mode replays the step as three captured segments,
     # [stages before the dominant kernel] [the dominant kernel] [the rest], with HIP events
@@ -242,7 +267,10 @@ def main():
 
         def one_step(k):
             cur[0] = k
-            fe.step(mark)
+            if pipelined:
+                fe.step_pipelined(mark, fork_after=dominant)
+            else:
+                fe.step(mark)
     else:
         pre, post = fe.split(dominant)
         g_pre = fe.capture(pre) if pre else None
@@ -272,6 +300,17 @@ def main():
     t1 = time.perf_counter()
     ms_step = (t1 - t0) * 1e3 / K
     dom_ms = sum(dev0[k].elapsed_time(dev1[k]) for k in range(K)) / K
+    ms_serial = None
+    if pipelined:
+        # the same K steps with each batch's unique inside its own step, for comparison
+        for _ in range(2):
+            fe.step()
+        torch.cuda.synchronize()
+        t2 = time.perf_counter()
+        for _ in range(K):
+            fe.step()
+        torch.cuda.synchronize()
+        ms_serial = (time.perf_counter() - t2) * 1e3 / K
 
     step_bytes = sum(byts.values())
     value = w.nnz / (ms_step * 1e-3)
@@ -288,7 +327,13 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16" if w.dtype == "bf16" else "f32",
-        "launch": "eager" if (not args.graph) else "hip-graph segments",
+        "launch": ("eager up to the dominant kernel, then captured graphs (the next batch's "
+                   "unique on a side stream; the rest of the step)" if pipelined else
+                   "eager" if (not args.graph) else "hip-graph segments"),
+        "schedule": ("pipelined: batch k+1's ID dedup runs during step k on a second stream "
+                     "(double-buffered outputs); every call runs once per step"
+                     if pipelined else "serial: each step dedups its own batch"),
+        "ms_per_step_serial": ms_serial if pipelined else ms_step,
         "data": "synthetic (seeded; tables from the counter-based fill)",
         "config": {"workload": WORKLOAD_NAMES[args.config], "name": args.config,
                    "batch": w.batch, "tables": w.num_tables, "dim": w.dim, "nnz": w.nnz,

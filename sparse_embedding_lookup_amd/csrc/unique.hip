@@ -381,71 +381,89 @@ __global__ __launch_bounds__(1024) void heads_scan_kernel(uint32_t* __restrict__
 }
 
 // sorted_src[p] = (distinct-row index of position p, bag of its occurrence, key as two
-// words); without bags the occurrence is its own bag.  FUSED: the block sums the head counts of the tiles before
-// it itself (few tiles), and the last block publishes U.
+// words); without bags the occurrence is its own bag.  Every load of the tile is issued
+// first (keys, the key before each position, occurrence, bag; and, when FUSED, the head
+// counts of the earlier tiles), then one barrier publishes the per-round wave head counts.
+// FUSED: few tiles, so the block sums the head counts of the tiles before it itself, and
+// the last block publishes U.
 template <typename K, bool FUSED>
 __global__ __launch_bounds__(kThreads) void unique_finalize_kernel(
     const K* __restrict__ sk, const uint32_t* __restrict__ sv, const uint32_t* __restrict__ sbag,
     int64_t n, uint64_t flip, const uint32_t* __restrict__ tile_heads, int64_t ntiles,
     int64_t* __restrict__ uniq, int32_t* __restrict__ inverse, int32_t* __restrict__ seg_offsets,
     int4* __restrict__ sorted_src, int32_t* __restrict__ num_unique) {
-  __shared__ uint32_t wsum[4];
+  __shared__ uint32_t wcnt[kFinRounds][4];
+  __shared__ uint32_t wtile[2][4];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const uint64_t le = (lane == 63) ? ~0ull : ((2ull << lane) - 1ull);
   const int64_t t0 = (int64_t)blockIdx.x * kFinTile;
-  uint32_t base;                                  // heads before this tile
+
+  K key[kFinRounds];
+  K prev[kFinRounds];
+  uint32_t occ[kFinRounds];
+  uint32_t bag[kFinRounds];
+#pragma unroll
+  for (int j = 0; j < kFinRounds; ++j) {
+    const int64_t p = t0 + (int64_t)j * kThreads + threadIdx.x;
+    const bool ok = p < n;
+    key[j] = ok ? sk[p] : (K)0;
+    prev[j] = (ok && p > 0) ? sk[p - 1] : (K)0;
+    occ[j] = ok ? sv[p] : 0u;
+    bag[j] = (ok && sbag) ? sbag[p] : occ[j];
+  }
+  uint32_t before_tile = 0, all_tiles = 0;
   if (FUSED) {
-    uint32_t s = 0, all = 0;
     for (int64_t t = threadIdx.x; t < ntiles; t += kThreads) {
       const uint32_t c = tile_heads[t];
-      all += c;
-      if (t < (int64_t)blockIdx.x) s += c;
+      all_tiles += c;
+      if (t < (int64_t)blockIdx.x) before_tile += c;
     }
-    // block sums of s and all
     for (int o = 32; o > 0; o >>= 1) {
-      s += __shfl_xor(s, o, 64);
-      all += __shfl_xor(all, o, 64);
+      before_tile += __shfl_xor(before_tile, o, 64);
+      all_tiles += __shfl_xor(all_tiles, o, 64);
     }
-    if (lane == 0) wsum[wave] = s;
-    __syncthreads();
-    base = wsum[0] + wsum[1] + wsum[2] + wsum[3];
-    __syncthreads();
-    if (lane == 0) wsum[wave] = all;
-    __syncthreads();
-    const uint32_t tot = wsum[0] + wsum[1] + wsum[2] + wsum[3];
-    __syncthreads();
+    if (lane == 0) {
+      wtile[0][wave] = before_tile;
+      wtile[1][wave] = all_tiles;
+    }
+  }
+  uint64_t m[kFinRounds];
+#pragma unroll
+  for (int j = 0; j < kFinRounds; ++j) {
+    const int64_t p = t0 + (int64_t)j * kThreads + threadIdx.x;
+    const bool h = p < n && (p == 0 || key[j] != prev[j]);
+    m[j] = __ballot(h);
+    if (lane == 0) wcnt[j][wave] = (uint32_t)__popcll(m[j]);
+  }
+  __syncthreads();
+  uint32_t base;
+  if (FUSED) {
+    base = wtile[0][0] + wtile[0][1] + wtile[0][2] + wtile[0][3];
     if (blockIdx.x == gridDim.x - 1 && threadIdx.x == 0) {
+      const uint32_t tot = wtile[1][0] + wtile[1][1] + wtile[1][2] + wtile[1][3];
       *num_unique = (int32_t)tot;
       if (seg_offsets) seg_offsets[tot] = (int32_t)n;
     }
   } else {
     base = tile_heads[blockIdx.x];
   }
+#pragma unroll
   for (int j = 0; j < kFinRounds; ++j) {
     const int64_t p = t0 + (int64_t)j * kThreads + threadIdx.x;
-    K k = 0;
-    const bool h = is_head(sk, p, n, &k);
-    const uint64_t m = __ballot(h);
-    if (lane == 0) wsum[wave] = (uint32_t)__popcll(m);
-    __syncthreads();
     uint32_t before = base;
-    for (int w = 0; w < wave; ++w) before += wsum[w];
-    const uint32_t total = wsum[0] + wsum[1] + wsum[2] + wsum[3];
-    __syncthreads();
+    for (int w = 0; w < wave; ++w) before += wcnt[j][w];
+    base += wcnt[j][0] + wcnt[j][1] + wcnt[j][2] + wcnt[j][3];
     if (p < n) {
-      const uint32_t r = before + (uint32_t)__popcll(m & le) - 1u;   // heads <= p, minus one
-      const uint64_t key = (uint64_t)k ^ flip;
-      if (h) {
-        uniq[r] = (int64_t)key;
+      const uint32_t r = before + (uint32_t)__popcll(m[j] & le) - 1u;   // heads <= p, less one
+      const uint64_t kk = (uint64_t)key[j] ^ flip;
+      if ((m[j] >> lane) & 1ull) {
+        uniq[r] = (int64_t)kk;
         if (seg_offsets) seg_offsets[r] = (int32_t)p;
       }
-      const uint32_t occ = sv[p];
-      if (occ < (uint64_t)n) inverse[occ] = (int32_t)r;
+      if (occ[j] < (uint64_t)n) inverse[occ[j]] = (int32_t)r;
       if (sorted_src)
-        sorted_src[p] = make_int4((int32_t)r, (int32_t)(sbag ? sbag[p] : occ), (int32_t)key,
-                                  (int32_t)(key >> 32));
+        sorted_src[p] = make_int4((int32_t)r, (int32_t)bag[j], (int32_t)kk, (int32_t)(kk >> 32));
     }
-    base += total;
   }
 }
 

@@ -32,11 +32,14 @@ class FrontEnd:
     """Device state for one workload: the tables, the batch and every buffer of the path."""
 
     def __init__(self, w: Workload, device="cuda", table: Optional[torch.Tensor] = None,
-                 fused: bool = True, keep_grads: bool = False):
+                 fused: bool = True, keep_grads: bool = False, pipelined: bool = False):
         """fused: the backward applies the sparse SGD as each row gradient completes
         (ctr_embbag_bwd_sgd); otherwise ctr_embbag_bwd then ctr_sparse_sgd.  keep_grads: also
-        keep the per-row gradients in self.row_grads (always kept when not fused)."""
+        keep the per-row gradients in self.row_grads (always kept when not fused).
+        pipelined: the unique outputs are double-buffered so that step_pipelined() can
+        deduplicate the next batch's IDs while the current batch trains."""
         self.w = w
+        self.pipelined = pipelined
         self.fused = fused
         self.keep_grads = keep_grads or not fused
         self.device = torch.device(device)
@@ -72,16 +75,33 @@ class FrontEnd:
                                      device=dv)
         self.ws_bwd = torch.empty(max(ctr.embbag_bwd_workspace_bytes(n, d), 256),
                                   dtype=torch.uint8, device=dv)
-        self.uniq = torch.empty(max(n, 1), dtype=torch.int64, device=dv)
-        self.inverse = torch.empty(max(n, 1), dtype=torch.int32, device=dv)
-        self.num_unique = torch.zeros(1, dtype=torch.int32, device=dv)
-        self.perm = torch.empty(max(n, 1), dtype=torch.int32, device=dv)
-        self.seg = torch.empty(n + 1, dtype=torch.int32, device=dv)
-        self.sorted_src = torch.empty((max(n, 1), 4), dtype=torch.int32, device=dv)
-        self._unique_out = (self.uniq, self.inverse, self.num_unique, self.perm, self.seg)
+        self._sets = [self._unique_buffers(n, dv) for _ in range(2 if pipelined else 1)]
+        self._calls = []
         self.side = None
+        self._k = 0
+        for i in range(len(self._sets)):
+            self._use_set(i)
+            self._prepare()
+            self._calls.append({k: v for k, v in self.__dict__.items() if k.startswith("_c_")})
+        self._use_set(0)
 
-        self._prepare()
+    @staticmethod
+    def _unique_buffers(n, dv):
+        return dict(uniq=torch.empty(max(n, 1), dtype=torch.int64, device=dv),
+                    inverse=torch.empty(max(n, 1), dtype=torch.int32, device=dv),
+                    num_unique=torch.zeros(1, dtype=torch.int32, device=dv),
+                    perm=torch.empty(max(n, 1), dtype=torch.int32, device=dv),
+                    seg=torch.empty(n + 1, dtype=torch.int32, device=dv),
+                    sorted_src=torch.empty((max(n, 1), 4), dtype=torch.int32, device=dv))
+
+    def _use_set(self, i):
+        """Point the unique outputs, and the prepared calls that use them, at set i."""
+        for k, v in self._sets[i].items():
+            setattr(self, k, v)
+        self._unique_out = (self.uniq, self.inverse, self.num_unique, self.perm, self.seg)
+        if len(self._calls) > i:
+            for k, v in self._calls[i].items():
+                setattr(self, k, v)
 
     # ------------------------------------------------------------------ steps of the path
     def _prepare(self):
@@ -235,6 +255,88 @@ class FrontEnd:
             else:
                 post = post + ["unique"]
         return pre, post
+
+    # ------------------------------------------------------------ pipelined schedule
+    def pipeline_start(self):
+        """Deduplicate the first batch; then call step_pipelined() once per batch."""
+        assert self.pipelined, "FrontEnd(pipelined=True) required"
+        if self.side is None:
+            self.side = torch.cuda.Stream(device=self.device)
+        self._k = 0
+        self._use_set(0)
+        self.unique()
+
+    def capture_pipelined_parts(self, fork_after: str):
+        """Graphs for a pipelined step, one of each per buffer set: the unique (replayed on the
+        side stream) and the main-stream stages after `fork_after` (replayed on the current
+        stream).  The stages up to `fork_after` stay eager, so HIP events can bracket them;
+        step_pipelined() then forks the next batch's unique right after them."""
+        if self.side is None:
+            self.side = torch.cuda.Stream(device=self.device)
+        names = [n for n, _ in self.stages() if n != "unique"]
+        i = names.index(fork_after) + 1
+        self._fork_after = fork_after
+        self._eager_names, rest = names[:i], names[i:]
+        self._g_unique, self._g_rest = [], []
+        for cur in range(len(self._sets)):
+            self._use_set(cur)
+            self._g_unique.append(self.capture(["unique"]))
+            self._g_rest.append(self.capture(rest) if rest else None)
+        self._use_set(0)
+
+    def step_pipelined(self, mark=None, k: Optional[int] = None,
+                       fork_after: Optional[str] = None):
+        """Step k of a stream of batches: batch k trains on the unique outputs computed during
+        step k-1 (set k % 2) while batch k+1's unique fills the other set on the side stream,
+        forked when the step starts (or right after stage `fork_after`) and joined when it
+        ends.  Every call of the path runs exactly once per step.  (The synthetic stream
+        repeats one batch, so batch k+1 holds the same IDs.)  After capture_pipelined_parts()
+        the unique and the stages after the fork replay from the graphs of their sets."""
+        go = mark if mark is not None else (lambda name, fn: fn())
+        if k is None:
+            k = self._k
+        cur, nxt = k & 1, (k + 1) & 1
+        main = torch.cuda.current_stream(self.device)
+        graphs = getattr(self, "_g_unique", None)
+        if graphs:
+            fork_after = self._fork_after
+        self._k = k + 1
+
+        def fork():
+            self.side.wait_stream(main)
+            with torch.cuda.stream(self.side):
+                if graphs:
+                    graphs[nxt].replay()
+                else:
+                    self._use_set(nxt)
+                    self.unique()
+            self._use_set(cur)
+
+        self._use_set(cur)
+        if fork_after is None:
+            fork()
+        for n, fn in self.stages():
+            if n == "unique" or (graphs and n not in self._eager_names):
+                continue
+            go(n, fn)
+            if n == fork_after:
+                fork()
+        if graphs and self._g_rest[cur] is not None:
+            self._g_rest[cur].replay()
+        main.wait_stream(self.side)
+
+    def capture_pipelined(self, steps: int = 2):
+        """Record `steps` (even) consecutive pipelined steps, starting with an even step, into
+        one HIP graph; each replay continues the stream of batches."""
+        assert steps % 2 == 0
+        if self.side is None:
+            self.side = torch.cuda.Stream(device=self.device)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for k in range(steps):
+                self.step_pipelined(k=k)
+        self._k = 0
+        return g
 
     def capture(self, names=None, steps: int = 1):
         """Record `steps` repetitions of the named stages (default: the whole step) into one

@@ -521,3 +521,38 @@ def test_fused_backward_sgd_matches_two_calls(name):
     U = int(host(fa.num_unique)[0])
     np.testing.assert_array_equal(host(fa.row_grads)[:U], host(fb.row_grads)[:U])
     assert torch.equal(fa.table, fb.table)          # whole table, compared on the device
+
+
+@pytest.mark.parametrize("graphs", [False, True])
+@pytest.mark.parametrize("name", ["small_b256", "criteo_b128", "tensornet_b512"])
+def test_pipelined_schedule_matches_serial(name, graphs):
+    """Deduplicating batch k+1 during step k (double-buffered unique outputs) leaves the
+    table, the forward outputs and the row gradients bit-identical to the serial steps, after
+    every step; with graphs, everything after the pooling (the next batch's unique on the
+    side stream included) replays from captured graphs, with unrelated eager work and
+    synchronizations between the steps."""
+    w = {"small_b256": lambda: workloads.small(batch=256),
+         "criteo_b128": lambda: workloads.criteo(batch=128),
+         "tensornet_b512": lambda: workloads.tensornet(batch=512, slots=100,
+                                                       table_rows=500_000)}[name]()
+    say("pipelined schedule", name, "graphs" if graphs else "eager")
+    fa = FrontEnd(w, DEV, keep_grads=True)
+    fb = FrontEnd(w, DEV, keep_grads=True, pipelined=True)
+    if graphs:
+        fb.capture_pipelined_parts(fork_after="embbag_fwd")
+    fb.pipeline_start()
+    junk = torch.randn(1 << 20, device=DEV)
+    for _ in range(4):
+        fa.step()
+        fb.step_pipelined(fork_after="embbag_fwd" if graphs else None)
+        junk.mul_(1.0001).add_(1.0)
+        torch.cuda.synchronize()
+        U = int(host(fa.num_unique)[0])
+        assert U == int(host(fb.num_unique)[0])
+        np.testing.assert_array_equal(host(fa.uniq)[:U], host(fb.uniq)[:U])
+        np.testing.assert_array_equal(host(fa.row_grads)[:U], host(fb.row_grads)[:U])
+        if w.interaction:
+            np.testing.assert_array_equal(host(fa.R), host(fb.R))
+        else:
+            np.testing.assert_array_equal(host(fa.out), host(fb.out))
+        assert torch.equal(fa.table, fb.table)
