@@ -19,11 +19,11 @@ buffers; each timed step still launches every call of the path once.
 The next batch's unique (side stream) and the main-stream stages after the dominant kernel
 replay from captured graphs to take the host's launch cost off the step; the stages up to
 the dominant kernel stay eager, so that HIP events on its stream time it in place.  "serial"
-dedups each batch inside its own step (eager); the pipelined run also reports that
-schedule's ms per step.
+dedups each batch inside its own step (eager); --compare-serial adds that schedule's ms per
+step to a pipelined run.
 
     python bench.py [--config small|tiny|criteo|tensornet|large] [--steps K] [--warmup W]
-                    [--schedule pipelined|serial] [--graph]
+                    [--schedule pipelined|serial] [--compare-serial] [--graph]
 """
 from __future__ import annotations
 
@@ -181,6 +181,8 @@ def main():
     ap.add_argument("--schedule", default="pipelined", choices=["pipelined", "serial"],
                     help="pipelined: batch k+1's ID dedup runs during step k (double-buffered "
                          "outputs); serial: every step dedups its own batch first")
+    ap.add_argument("--compare-serial", action="store_true",
+                    help="after a pipelined run, also time K serial steps (ms_per_step_serial)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -210,8 +212,14 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    for _ in range(args.warmup):
-        fe.step()
+    first_main = next(n for n, _ in st if n != "unique")
+    if pipelined:
+        fe.pipeline_start()
+        for _ in range(args.warmup):
+            fe.step_pipelined(fork_after=first_main)
+    else:
+        for _ in range(args.warmup):
+            fe.step()
     torch.cuda.synchronize()
     U = int(fe.num_unique.cpu()[0])
 
@@ -236,7 +244,9 @@ def main():
     torch.cuda.synchronize()
     stage_ms = {n: sum(e0.elapsed_time(e1) for e0, e1 in evs[n]) / K for n in names}
     byts = stage_bytes(w, U)
-    dominant = max((s for s in stage_ms if s in SINGLE_KERNEL), key=lambda s: stage_ms[s])
+    # the roofline's kernel: the single-kernel stage that moves the most algorithmic bytes
+    # (the pooled gather on every workload); fixed by the workload, not by a timing
+    dominant = max((s for s in stage_ms if s in SINGLE_KERNEL), key=lambda s: byts[s])
     if pipelined:
         # the next batch's unique and the stages after the dominant kernel replay from captured
         # graphs (host launch cost); the stages up to the dominant one stay eager so that HIP
@@ -301,7 +311,7 @@ def main():
     ms_step = (t1 - t0) * 1e3 / K
     dom_ms = sum(dev0[k].elapsed_time(dev1[k]) for k in range(K)) / K
     ms_serial = None
-    if pipelined:
+    if pipelined and args.compare_serial:
         # the same K steps with each batch's unique inside its own step, for comparison
         for _ in range(2):
             fe.step()
@@ -333,7 +343,7 @@ def main():
         "schedule": ("pipelined: batch k+1's ID dedup runs during step k on a second stream "
                      "(double-buffered outputs); every call runs once per step"
                      if pipelined else "serial: each step dedups its own batch"),
-        "ms_per_step_serial": ms_serial if pipelined else ms_step,
+        "ms_per_step_serial": ms_serial if pipelined else ms_step,   # null unless compared
         "data": "synthetic (seeded; tables from the counter-based fill)",
         "config": {"workload": WORKLOAD_NAMES[args.config], "name": args.config,
                    "batch": w.batch, "tables": w.num_tables, "dim": w.dim, "nnz": w.nnz,
