@@ -15,15 +15,21 @@ sample of the same workload.
 Schedule (default "pipelined"): training consumes a stream of batches, and the ID dedup of
 batch k+1 needs only that batch's IDs, so it runs on a second stream during step k (forked
 right after the dominant kernel, which thus runs alone) into a second set of output
-buffers; each timed step still launches every call of the path once.
-The next batch's unique (side stream) and the main-stream stages after the dominant kernel
-replay from captured graphs to take the host's launch cost off the step; the stages up to
-the dominant kernel stay eager, so that HIP events on its stream time it in place.  "serial"
-dedups each batch inside its own step (eager); --compare-serial adds that schedule's ms per
-step to a pipelined run.
+buffers; each timed step still launches every call of the path once.  "serial" dedups each
+batch inside its own step; --compare-serial adds that schedule's ms per step to a pipelined
+run.
+
+Launch (default "graph"): ctr_step_run enqueues a whole step from C++ (every kernel, the
+fork/join of the side stream, and HIP events around the pooling kernel on its stream); the K
+timed steps are captured once as one HIP graph, the timing events as event-record nodes, and
+the graph is replayed, so the host's launch cost (about 2.5 us per kernel and 10 us per
+cross-stream wait on this stack) stays off the steps.  "native" calls ctr_step_run once per
+step; "python" makes one binding call per stage (the pipelined schedule then replays the next
+batch's unique and the stages after the pooling kernel from captured graphs).
 
     python bench.py [--config small|tiny|criteo|tensornet|large] [--steps K] [--warmup W]
-                    [--schedule pipelined|serial] [--compare-serial] [--graph]
+                    [--schedule pipelined|serial] [--compare-serial]
+                    [--launch native|python|graph]
 """
 from __future__ import annotations
 
@@ -176,8 +182,11 @@ def main():
     ap.add_argument("--detail", default="", help="write per-stage detail JSON here")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MB",
                     help="run one device copy of MB MiB first (scale for HBM byte counters)")
-    ap.add_argument("--graph", action="store_true",
-                    help="replay captured HIP graph segments instead of launching from the host")
+    ap.add_argument("--launch", default="graph", choices=["graph", "native", "python"],
+                    help="graph: the K timed steps, enqueued by ctr_step_run under stream "
+                         "capture, replayed as one HIP graph; native: one ctr_step_run call per "
+                         "step; python: one binding call per stage (with captured graph parts "
+                         "when pipelined)")
     ap.add_argument("--schedule", default="pipelined", choices=["pipelined", "serial"],
                     help="pipelined: batch k+1's ID dedup runs during step k (double-buffered "
                          "outputs); serial: every step dedups its own batch first")
@@ -197,7 +206,11 @@ def main():
     print("[bench] generating workload %s" % args.config, file=sys.stderr, flush=True)
     w = workloads.make(args.config)
     print("[bench] nnz=%d, building device state" % w.nnz, file=sys.stderr, flush=True)
-    pipelined = args.schedule == "pipelined" and not args.graph
+    graph = args.launch == "graph"
+    native = args.launch in ("native", "graph")
+    pipelined = args.schedule == "pipelined"
+    if graph and pipelined and args.steps % 2:
+        args.steps += 1                  # a pipelined graph holds whole pairs of steps
     fe = FrontEnd(w, "cuda", pipelined=pipelined)
     st = fe.stages()
     torch.cuda.synchronize()
@@ -213,26 +226,31 @@ def main():
         del src, dst
 
     first_main = next(n for n, _ in st if n != "unique")
-    if pipelined:
-        fe.pipeline_start()
-        for _ in range(args.warmup):
-            fe.step_pipelined(fork_after=first_main)
-    else:
-        for _ in range(args.warmup):
-            fe.step()
-    torch.cuda.synchronize()
+
+    def warm():
+        if native:
+            if pipelined:
+                fe.native_start()
+            for _ in range(args.warmup):
+                fe.step_native(pipelined)
+        elif pipelined:
+            fe.pipeline_start()
+            for _ in range(args.warmup):
+                fe.step_pipelined(fork_after=first_main)
+        else:
+            for _ in range(args.warmup):
+                fe.step()
+        torch.cuda.synchronize()
+
+    warm()
     U = int(fe.num_unique.cpu()[0])
 
     K = args.steps
 
-    # Per-stage durations (diagnostic, before the timed region): each stage alone, as a
-    # captured graph in graph mode, bracketed by HIP events on the stream it runs on.
+    # Per-stage durations (diagnostic, before the timed region): each stage alone, bracketed
+    # by HIP events on the stream it runs on.
     names = [n for n, _ in st]
-    if (not args.graph):
-        stage_runs = {n: (lambda n=n: fe.run([n])) for n in names}
-    else:
-        stage_graphs = {n: fe.capture([n]) for n in names}
-        stage_runs = {n: stage_graphs[n].replay for n in names}
+    stage_runs = {n: (lambda n=n: fe.run([n])) for n in names}
     evs = {n: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                for _ in range(K)] for n in names}
     for k in range(K):
@@ -247,7 +265,11 @@ def main():
     # the roofline's kernel: the single-kernel stage that moves the most algorithmic bytes
     # (the pooled gather on every workload); fixed by the workload, not by a timing
     dominant = max((s for s in stage_ms if s in SINGLE_KERNEL), key=lambda s: byts[s])
-    if pipelined:
+    if native:
+        # ctr_step_run brackets the pooling kernel with the timing events
+        assert dominant == "embbag_fwd", dominant
+        warm()
+    elif pipelined:
         # the next batch's unique and the stages after the dominant kernel replay from captured
         # graphs (host launch cost); the stages up to the dominant one stay eager so that HIP
         # events on the main stream bracket the dominant kernel itself
@@ -257,68 +279,72 @@ def main():
             fe.step_pipelined(fork_after=dominant)
         torch.cuda.synchronize()
 
-    # Timed region: K whole steps.  Graph mode replays the step as three captured segments,
-    # [stages before the dominant kernel] [the dominant kernel] [the rest], with HIP events
-    # recorded between the launches, on the stream the dominant kernel runs on.
-    print("[bench] timing %d steps (%s)" % (K, "eager" if (not args.graph) else "graph"),
-          file=sys.stderr, flush=True)
+    # Timed region: K whole steps, bracketed by device synchronizations.  The HIP events
+    # dev0[k], dev1[k] bracket step k's pooling kernel on its stream (in graph mode as
+    # event-record nodes of the captured steps, so the replay leaves them timed).
+    print("[bench] timing %d steps (%s, %s)" % (K, args.launch, "pipelined" if pipelined
+                                                else "serial"), file=sys.stderr, flush=True)
     dev0 = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
     dev1 = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
-    if (not args.graph):
-        cur = [0]
-
-        def mark(name, fn):
-            if name == dominant:
-                dev0[cur[0]].record()
-                fn()
-                dev1[cur[0]].record()
-            else:
-                fn()
-
-        def one_step(k):
-            cur[0] = k
-            if pipelined:
-                fe.step_pipelined(mark, fork_after=dominant)
-            else:
-                fe.step(mark)
+    for e in dev0 + dev1:
+        e.record()                       # torch creates the HIP event on its first record
+    torch.cuda.synchronize()
+    if graph:
+        g_steps = fe.capture_native(K, pipelined, [e for pair in zip(dev0, dev1) for e in pair])
+        if pipelined:
+            fe.native_start()
+        g_steps.replay()                 # warm replay
+        if pipelined:
+            fe.native_start()            # set 0 for the first step (the unique of the step
+                                         # before; the graph's last step fills it again)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        g_steps.replay()
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
     else:
-        pre, post = fe.split(dominant)
-        g_pre = fe.capture(pre) if pre else None
-        g_dom = fe.capture([dominant])
-        g_post = fe.capture(post) if post else None
-        for _ in range(args.warmup):
-            if g_pre:
-                g_pre.replay()
-            g_dom.replay()
-            if g_post:
-                g_post.replay()
+        if native:
+            def one_step(k):
+                fe.step_native(pipelined, dev0[k], dev1[k])
+        else:
+            def mark(name, fn):
+                if name == dominant:
+                    dev0[cur[0]].record()
+                    fn()
+                    dev1[cur[0]].record()
+                else:
+                    fn()
 
-        def one_step(k):
-            if g_pre:
-                g_pre.replay()
-            dev0[k].record()
-            g_dom.replay()
-            dev1[k].record()
-            if g_post:
-                g_post.replay()
+            cur = [0]
 
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for k in range(K):
-        one_step(k)
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
+            def one_step(k):
+                cur[0] = k
+                if pipelined:
+                    fe.step_pipelined(mark, fork_after=dominant)
+                else:
+                    fe.step(mark)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for k in range(K):
+            one_step(k)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
     ms_step = (t1 - t0) * 1e3 / K
     dom_ms = sum(dev0[k].elapsed_time(dev1[k]) for k in range(K)) / K
     ms_serial = None
     if pipelined and args.compare_serial:
         # the same K steps with each batch's unique inside its own step, for comparison
-        for _ in range(2):
-            fe.step()
+        if graph:
+            g_ser = fe.capture_native(K, False)
+            serial_steps = [g_ser.replay]
+        else:
+            serial_steps = [(lambda: fe.step_native(False)) if native else fe.step] * K
+        for f in serial_steps[:2]:
+            f()
         torch.cuda.synchronize()
         t2 = time.perf_counter()
-        for _ in range(K):
-            fe.step()
+        for f in serial_steps:
+            f()
         torch.cuda.synchronize()
         ms_serial = (time.perf_counter() - t2) * 1e3 / K
 
@@ -337,9 +363,10 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16" if w.dtype == "bf16" else "f32",
-        "launch": ("eager up to the dominant kernel, then captured graphs (the next batch's "
-                   "unique on a side stream; the rest of the step)" if pipelined else
-                   "eager" if (not args.graph) else "hip-graph segments"),
+        "launch": ("hip graph of the K timed steps, captured from ctr_step_run" if graph else
+                   "native: one ctr_step_run call enqueues the whole step" if native else
+                   "eager up to the dominant kernel, then captured graphs (the next batch's "
+                   "unique on a side stream; the rest of the step)" if pipelined else "eager"),
         "schedule": ("pipelined: batch k+1's ID dedup runs during step k on a second stream "
                      "(double-buffered outputs); every call runs once per step"
                      if pipelined else "serial: each step dedups its own batch"),

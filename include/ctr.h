@@ -222,6 +222,92 @@ int32_t ctr_validate_csr(const void* indices, int32_t index_type, int64_t nnz,
                          const int64_t* row_base, int64_t total_rows, int32_t* bad_count,
                          void* stream);
 
+/*
+ * ---------------------------------------------------------------- one training step
+ * ctr_step_t describes every device buffer of one training step of the front end; the
+ * caller owns all of it (the library keeps no state and allocates nothing).  Two kinds:
+ *
+ *   CTR_STEP_POOLED_INTERACTION  tables + dense vector ("Meta DLRM" 02, "DHEN" notes 2.1):
+ *     ctr_unique_ids over (indices, offsets, row_base) -> ctr_embbag_fwd into Z[:, 1:, :]
+ *     -> ctr_dot_interaction_fwd (Z -> R) -> ctr_dot_interaction_bwd (dR -> dZ)
+ *     -> ctr_embbag_bwd_sgd over dZ[:, 1:, :] (SGD on the touched rows).
+ *     Z, dZ: fp32 [batch, num_tables + 1, dim], Z[:, 0, :] = the dense vector (input);
+ *     R, dR: fp32 [batch, dim + P], P = (num_tables + 1) * num_tables / 2.
+ *   CTR_STEP_BATCH_MATRIX  one table, IDs mapped by key_modulus ([TN] "Core Optimizations"):
+ *     ctr_unique_ids(indices mod key_modulus) -> ctr_gather_rows into E -> ctr_embbag_fwd over
+ *     E with the inverse map (one ID per bag, offsets = 0..nnz) into out
+ *     -> ctr_embbag_bwd_sgd over dout (SGD on the touched table rows).
+ *     E, out, dout: fp32 [nnz, dim].
+ *
+ * Unique outputs exist twice (index 0 and 1) for the pipelined schedule; the serial
+ * schedule uses index 0 only (index 1 may repeat index 0).  Each array has capacity nnz
+ * (seg_offsets nnz + 1; sorted_src 4 int32 per position, 16-byte aligned).  Workspaces are
+ * sized by the two-call queries of ctr_unique_ids and ctr_embbag_bwd.  row_grads
+ * (fp32 [nnz, dim]) is optional.
+ */
+enum { CTR_STEP_POOLED_INTERACTION = 0, CTR_STEP_BATCH_MATRIX = 1 };
+enum { CTR_SCHEDULE_SERIAL = 0, CTR_SCHEDULE_PIPELINED = 1 };
+
+typedef struct {
+  int32_t kind;
+  int32_t index_type;             /* CTR_I32 or CTR_I64 */
+  const void* indices;            /* [nnz] */
+  int64_t nnz;
+  const int64_t* offsets;         /* [num_tables*batch + 1] (pooled) or [nnz + 1] */
+  int64_t batch;
+  int32_t num_tables;
+  int32_t dim;
+  const int64_t* row_base;        /* device [num_tables + 1] (pooled step) */
+  int64_t key_modulus;            /* batch-matrix step */
+  void* table;
+  int32_t dtype;                  /* CTR_F32 or CTR_BF16 */
+  int32_t compute;                /* interaction arithmetic, CTR_F32 or CTR_BF16 */
+  int64_t total_rows;
+  float lr;
+  float* Z;
+  float* R;
+  const float* dR;
+  float* dZ;
+  float* E;
+  float* out;
+  const float* dout;
+  float* row_grads;
+  void* ws_unique;
+  size_t ws_unique_bytes;
+  void* ws_bwd;
+  size_t ws_bwd_bytes;
+  int64_t* uniq[2];
+  int32_t* inverse[2];
+  int32_t* num_unique[2];
+  int32_t* perm[2];               /* nullable */
+  int32_t* seg_offsets[2];        /* nullable */
+  int32_t* sorted_src[2];
+} ctr_step_t;
+
+/*
+ * ctr_step_run -- enqueue training step k on main_stream (one C call for the whole chain).
+ *   CTR_SCHEDULE_SERIAL     the batch's unique fills set 0 first; with a side stream the
+ *                           pooled step runs it there, beside the pooling and interaction,
+ *                           joined before the backward.
+ *   CTR_SCHEDULE_PIPELINED  step k trains on set k % 2, which ctr_step_unique (before the
+ *                           first step) or step k-1 filled; right after the pooling kernel the
+ *                           next batch's unique is forked to side_stream into the other set,
+ *                           and the step joins it before returning control of set k % 2.
+ *                           (With one repeated batch, the next batch is the same IDs.)
+ * fork_event / join_event: caller-created events (required with a side stream); mark_begin /
+ * mark_end: optional events recorded on main_stream right before and after the pooling
+ * kernel.  Under stream capture (graph building) the marks become event-record nodes of the
+ * graph, so that each replay leaves them timed.  Returns the first failing call's status;
+ * the calls before it stay enqueued.
+ */
+int32_t ctr_step_run(const ctr_step_t* step, int64_t k, int32_t schedule, void* main_stream,
+                     void* side_stream, void* fork_event, void* join_event, void* mark_begin,
+                     void* mark_end);
+
+/* ctr_step_unique -- the unique of the step's batch into set 0 or 1 on `stream` (primes
+ * the pipelined schedule). */
+int32_t ctr_step_unique(const ctr_step_t* step, int32_t set, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

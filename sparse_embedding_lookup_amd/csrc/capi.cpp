@@ -54,6 +54,10 @@ int32_t check_table(const void* table, int32_t dtype, int64_t total_rows, int32_
 
 }  // namespace
 
+namespace ctr {
+int32_t set_error(int32_t code, const char* msg) { return fail(code, "%s", msg); }
+}  // namespace ctr
+
 extern "C" {
 
 int32_t ctr_version(void) { return 100; }

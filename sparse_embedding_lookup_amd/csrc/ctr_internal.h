@@ -75,6 +75,9 @@ inline RowGeom row_geom(int64_t vecs) {
   return {G, VPL};
 }
 
+// Records the thread's ctr_last_error text and returns code (capi.cpp).
+int32_t set_error(int32_t code, const char* msg);
+
 // ----------------------------------------------------------------------------- launchers
 // Each returns hipSuccess or the launch error.  Shapes are validated by the caller.
 

@@ -1,0 +1,173 @@
+// step.cpp -- one training step of the sparse front end enqueued from native code: every
+// call of the path, the fork and join of the unique's side stream, and optional timing
+// events around the pooling kernel, in one C call (the per-call cost of an interpreter
+// would otherwise exceed the GPU time of a small batch).
+//
+// The step is the chain the pages describe: the batch's IDs deduplicated into contiguous
+// indices ("How TensorNet Supercharges Sparse Feature Training on TensorFlow", "Core
+// Optimizations"), sum-pooled lookups ("DHEN" notes, 2.1), the pairwise-dot interaction
+// ("Meta DLRM", 02), and the backward that updates only the rows present in the batch
+// (TensorNet page, "Synchronous Architecture").  Each call below is the public entry point
+// with its own checks; nothing here computes.
+#include <hip/hip_runtime.h>
+
+#include "../../include/ctr.h"
+#include "ctr_internal.h"
+
+namespace {
+
+int32_t invalid(const char* msg) { return ctr::set_error(CTR_ERR_INVALID_ARGUMENT, msg); }
+
+int32_t record(void* ev, hipStream_t s) {
+  if (!ev) return CTR_OK;
+  const hipError_t e = hipEventRecord(static_cast<hipEvent_t>(ev), s);
+  return e == hipSuccess ? CTR_OK : ctr::set_error(CTR_ERR_HIP, hipGetErrorString(e));
+}
+
+// A timing mark.  Under stream capture a recorded event cannot be timed afterwards, but an
+// event-record node added to the capture can: the node goes after the stream's current
+// capture dependencies and becomes the only one.
+int32_t mark(void* ev, hipStream_t s) {
+  if (!ev) return CTR_OK;
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  hipError_t e = hipStreamIsCapturing(s, &cs);
+  if (e != hipSuccess) return ctr::set_error(CTR_ERR_HIP, hipGetErrorString(e));
+  if (cs != hipStreamCaptureStatusActive) return record(ev, s);
+  hipStreamCaptureStatus st;
+  unsigned long long id;
+  hipGraph_t g;
+  const hipGraphNode_t* deps;
+  size_t ndeps;
+  hipGraphNode_t node;
+  e = hipStreamGetCaptureInfo_v2(s, &st, &id, &g, &deps, &ndeps);
+  if (e == hipSuccess)
+    e = hipGraphAddEventRecordNode(&node, g, deps, ndeps, static_cast<hipEvent_t>(ev));
+  if (e == hipSuccess)
+    e = hipStreamUpdateCaptureDependencies(s, &node, 1, hipStreamSetCaptureDependencies);
+  return e == hipSuccess ? CTR_OK : ctr::set_error(CTR_ERR_HIP, hipGetErrorString(e));
+}
+
+int32_t wait(hipStream_t s, void* ev) {
+  const hipError_t e = hipStreamWaitEvent(s, static_cast<hipEvent_t>(ev), 0);
+  return e == hipSuccess ? CTR_OK : ctr::set_error(CTR_ERR_HIP, hipGetErrorString(e));
+}
+
+#define CTR_TRY(x)                  \
+  do {                              \
+    const int32_t st_ = (x);        \
+    if (st_ != CTR_OK) return st_;  \
+  } while (0)
+
+int32_t unique_into(const ctr_step_t* d, int set, void* stream) {
+  size_t wsb = d->ws_unique_bytes;
+  if (d->kind == CTR_STEP_POOLED_INTERACTION)
+    return ctr_unique_ids(d->indices, d->index_type, d->nnz, d->offsets, d->batch,
+                          d->num_tables, d->row_base, d->total_rows, 0, d->uniq[set],
+                          d->inverse[set], d->num_unique[set], d->perm[set], d->seg_offsets[set],
+                          d->sorted_src[set], d->ws_unique, &wsb, stream);
+  return ctr_unique_ids(d->indices, d->index_type, d->nnz, nullptr, 0, 0, nullptr, 0,
+                        d->key_modulus, d->uniq[set], d->inverse[set], d->num_unique[set],
+                        d->perm[set], d->seg_offsets[set], d->sorted_src[set], d->ws_unique, &wsb,
+                        stream);
+}
+
+// The stages before the unique may fork (pooling, and for the batch-matrix step the gather).
+int32_t forward_part(const ctr_step_t* d, int set, hipStream_t s, void* mark_begin,
+                     void* mark_end) {
+  if (d->kind == CTR_STEP_POOLED_INTERACTION) {
+    const int64_t F = (int64_t)d->num_tables + 1;
+    CTR_TRY(mark(mark_begin, s));
+    CTR_TRY(ctr_embbag_fwd(d->table, d->dtype, d->total_rows, d->dim, d->row_base, d->num_tables,
+                           d->indices, d->index_type, d->nnz, d->offsets, d->batch,
+                           d->Z + d->dim, F * d->dim, d->dim, s));
+    return mark(mark_end, s);
+  }
+  CTR_TRY(ctr_gather_rows(d->table, d->dtype, d->total_rows, d->dim, d->uniq[set],
+                          d->num_unique[set], d->nnz, d->E, s));
+  CTR_TRY(mark(mark_begin, s));
+  CTR_TRY(ctr_embbag_fwd(d->E, CTR_F32, d->nnz, d->dim, nullptr, 1, d->inverse[set], CTR_I32,
+                         d->nnz, d->offsets, d->nnz, d->out, d->dim, 0, s));
+  return mark(mark_end, s);
+}
+
+// The rest of the step: interaction and its gradient (pooled step), then the backward with
+// the SGD update of the touched rows.
+int32_t backward_part(const ctr_step_t* d, int set, hipStream_t s, bool wait_unique,
+                      void* join_event) {
+  const int64_t F = (int64_t)d->num_tables + 1;
+  if (d->kind == CTR_STEP_POOLED_INTERACTION) {
+    CTR_TRY(ctr_dot_interaction_fwd(d->Z, d->batch, (int32_t)F, d->dim, d->compute, d->R,
+                                    d->dim + F * (F - 1) / 2, s));
+    CTR_TRY(ctr_dot_interaction_bwd(d->Z, d->dR, d->dim + F * (F - 1) / 2, d->batch, (int32_t)F,
+                                    d->dim, d->compute, d->dZ, s));
+  }
+  if (wait_unique) CTR_TRY(wait(s, join_event));
+  size_t wsb = d->ws_bwd_bytes;
+  if (d->kind == CTR_STEP_POOLED_INTERACTION)
+    return ctr_embbag_bwd_sgd(d->dZ + d->dim, F * d->dim, d->dim, d->offsets, d->batch,
+                              d->num_tables, d->nnz, d->sorted_src[set], d->num_unique[set],
+                              d->table, d->dtype, d->total_rows, d->dim, d->uniq[set], d->lr,
+                              d->row_grads, d->ws_bwd, &wsb, s);
+  return ctr_embbag_bwd_sgd(d->dout, d->dim, 0, d->offsets, d->nnz, 1, d->nnz,
+                            d->sorted_src[set], d->num_unique[set], d->table, d->dtype,
+                            d->total_rows, d->dim, d->uniq[set], d->lr, d->row_grads, d->ws_bwd,
+                            &wsb, s);
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t ctr_step_unique(const ctr_step_t* d, int32_t set, void* stream) {
+  if (!d) return invalid("step is NULL");
+  if (d->kind != CTR_STEP_POOLED_INTERACTION && d->kind != CTR_STEP_BATCH_MATRIX)
+    return invalid("unknown step kind");
+  if (set < 0 || set > 1) return invalid("set must be 0 or 1");
+  return unique_into(d, set, stream);
+}
+
+int32_t ctr_step_run(const ctr_step_t* d, int64_t k, int32_t schedule, void* main_stream,
+                     void* side_stream, void* fork_event, void* join_event, void* mark_begin,
+                     void* mark_end) {
+  if (!d) return invalid("step is NULL");
+  if (d->kind != CTR_STEP_POOLED_INTERACTION && d->kind != CTR_STEP_BATCH_MATRIX)
+    return invalid("unknown step kind");
+  if (k < 0) return invalid("step index k < 0");
+  if (schedule != CTR_SCHEDULE_SERIAL && schedule != CTR_SCHEDULE_PIPELINED)
+    return invalid("unknown schedule");
+  if (side_stream && (!fork_event || !join_event))
+    return invalid("a side stream needs fork and join events");
+  if (schedule == CTR_SCHEDULE_PIPELINED && !side_stream)
+    return invalid("the pipelined schedule needs a side stream");
+  hipStream_t s = static_cast<hipStream_t>(main_stream);
+  hipStream_t side = static_cast<hipStream_t>(side_stream);
+
+  if (schedule == CTR_SCHEDULE_SERIAL) {
+    // the batch's own unique first (beside the pooling and the interaction when the pooled
+    // step has a side stream), into set 0
+    const bool fork = side && d->kind == CTR_STEP_POOLED_INTERACTION;
+    if (fork) {
+      CTR_TRY(record(fork_event, s));
+      CTR_TRY(wait(side, fork_event));
+      CTR_TRY(unique_into(d, 0, side));
+      CTR_TRY(record(join_event, side));
+    } else {
+      CTR_TRY(unique_into(d, 0, s));
+    }
+    CTR_TRY(forward_part(d, 0, s, mark_begin, mark_end));
+    return backward_part(d, 0, s, fork, join_event);
+  }
+  // pipelined: batch k uses set k % 2 (filled during step k-1, or by ctr_step_unique before
+  // the first step); batch k+1's unique fills the other set on the side stream, forked after
+  // the pooling kernel and joined before the step ends
+  const int cur = (int)(k & 1), nxt = cur ^ 1;
+  CTR_TRY(forward_part(d, cur, s, mark_begin, mark_end));
+  CTR_TRY(record(fork_event, s));
+  CTR_TRY(wait(side, fork_event));
+  CTR_TRY(unique_into(d, nxt, side));
+  CTR_TRY(record(join_event, side));
+  CTR_TRY(backward_part(d, cur, s, false, join_event));
+  return wait(s, join_event);
+}
+
+}  // extern "C"

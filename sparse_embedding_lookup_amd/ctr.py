@@ -23,8 +23,28 @@ EXPORTED = [
     "ctr_version", "ctr_status_string", "ctr_last_error", "ctr_unique_ids", "ctr_gather_rows",
     "ctr_embbag_fwd", "ctr_embbag_bwd", "ctr_embbag_bwd_sgd", "ctr_sparse_sgd",
     "ctr_dot_interaction_fwd",
-    "ctr_dot_interaction_bwd", "ctr_init_table_hash", "ctr_validate_csr",
+    "ctr_dot_interaction_bwd", "ctr_init_table_hash", "ctr_validate_csr", "ctr_step_run",
+    "ctr_step_unique",
 ]
+
+CTR_STEP_POOLED_INTERACTION, CTR_STEP_BATCH_MATRIX = 0, 1
+CTR_SCHEDULE_SERIAL, CTR_SCHEDULE_PIPELINED = 0, 1
+
+
+class CtrStep(ctypes.Structure):
+    """ctr_step_t of include/ctr.h: every device buffer of one training step."""
+    _P = ctypes.c_void_p
+    _fields_ = [("kind", ctypes.c_int32), ("index_type", ctypes.c_int32), ("indices", _P),
+                ("nnz", ctypes.c_int64), ("offsets", _P), ("batch", ctypes.c_int64),
+                ("num_tables", ctypes.c_int32), ("dim", ctypes.c_int32), ("row_base", _P),
+                ("key_modulus", ctypes.c_int64), ("table", _P), ("dtype", ctypes.c_int32),
+                ("compute", ctypes.c_int32), ("total_rows", ctypes.c_int64),
+                ("lr", ctypes.c_float), ("Z", _P), ("R", _P), ("dR", _P), ("dZ", _P), ("E", _P),
+                ("out", _P), ("dout", _P), ("row_grads", _P), ("ws_unique", _P),
+                ("ws_unique_bytes", ctypes.c_size_t), ("ws_bwd", _P),
+                ("ws_bwd_bytes", ctypes.c_size_t), ("uniq", _P * 2), ("inverse", _P * 2),
+                ("num_unique", _P * 2), ("perm", _P * 2), ("seg_offsets", _P * 2),
+                ("sorted_src", _P * 2)]
 
 _lib = None
 
@@ -66,6 +86,8 @@ def load() -> ctypes.CDLL:
         "ctr_dot_interaction_bwd": (i32, [P, P, i64, i64, i32, i32, i32, P, P]),
         "ctr_init_table_hash": (i32, [P, i32, i32, P, i32, u64, P]),
         "ctr_validate_csr": (i32, [P, i32, i64, P, i64, i32, P, i64, P, P]),
+        "ctr_step_run": (i32, [P, i64, i32, P, P, P, P, P, P]),
+        "ctr_step_unique": (i32, [P, i32, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -302,3 +324,28 @@ def ctr_validate_csr(indices: torch.Tensor, offsets: torch.Tensor, batch: int, n
     _check("ctr_validate_csr", lib.ctr_validate_csr(
         _ptr(indices), _index_code(indices), indices.numel(), _ptr(offsets), batch, num_tables,
         _ptr(row_base), total_rows, _ptr(bad_count), _stream(stream)))
+
+
+def ctr_step_run(step: CtrStep, k: int, schedule: int, main_stream=None, side_stream=None,
+                 fork_event=None, join_event=None, mark_begin=None, mark_end=None) -> None:
+    """Enqueue training step k of ``step`` (a CtrStep) in one native call; the events are
+    torch.cuda.Event objects (fork/join required with a side stream)."""
+    ms = main_stream if main_stream is not None else torch.cuda.current_stream()
+
+    def ev(e):
+        if e is None:
+            return None
+        if not e.cuda_event:
+            e.record(ms)                  # torch creates the HIP event on its first record
+        return ctypes.c_void_p(e.cuda_event)
+
+    st = load().ctr_step_run(ctypes.byref(step), k, schedule, ctypes.c_void_p(ms.cuda_stream),
+                             None if side_stream is None else ctypes.c_void_p(
+                                 side_stream.cuda_stream),
+                             ev(fork_event), ev(join_event), ev(mark_begin), ev(mark_end))
+    _check("ctr_step_run", st)
+
+
+def ctr_step_unique(step: CtrStep, set_index: int, stream=None) -> None:
+    _check("ctr_step_unique", load().ctr_step_unique(ctypes.byref(step), set_index,
+                                                     _stream(stream)))

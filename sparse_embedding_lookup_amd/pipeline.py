@@ -338,6 +338,77 @@ class FrontEnd:
         self._k = 0
         return g
 
+    # ------------------------------------------------------------ native step
+    def native(self) -> ctr.CtrStep:
+        """The step's buffers as a ctr_step_t for ctr_step_run (built once)."""
+        if getattr(self, "_native", None) is not None:
+            return self._native
+        w = self.w
+        d = ctr.CtrStep()
+        P = lambda t: None if t is None else t.data_ptr()
+        d.kind = ctr.CTR_STEP_POOLED_INTERACTION if w.interaction else ctr.CTR_STEP_BATCH_MATRIX
+        d.index_type = ctr.CTR_I64 if self.indices.dtype == torch.int64 else ctr.CTR_I32
+        d.indices, d.nnz, d.offsets = P(self.indices), self.nnz, P(self.offsets)
+        d.batch, d.num_tables, d.dim = w.batch, w.num_tables, w.dim
+        d.row_base, d.key_modulus = P(self.row_base), w.key_modulus
+        d.table, d.dtype, d.compute = P(self.table), ctr._dtype_code(self.table), self.compute
+        d.total_rows, d.lr = w.total_rows, w.lr
+        if w.interaction:
+            d.Z, d.R, d.dR, d.dZ = P(self.Z), P(self.R), P(self.dR), P(self.dZ)
+        else:
+            d.E, d.out, d.dout = P(self.E), P(self.out), P(self.dout)
+        d.row_grads = P(self.row_grads)
+        d.ws_unique, d.ws_unique_bytes = P(self.ws_unique), self.ws_unique.numel()
+        d.ws_bwd, d.ws_bwd_bytes = P(self.ws_bwd), self.ws_bwd.numel()
+        for i in range(2):
+            b = self._sets[min(i, len(self._sets) - 1)]
+            d.uniq[i], d.inverse[i] = P(b["uniq"]), P(b["inverse"])
+            d.num_unique[i], d.perm[i] = P(b["num_unique"]), P(b["perm"])
+            d.seg_offsets[i], d.sorted_src[i] = P(b["seg"]), P(b["sorted_src"])
+        self._native = d
+        self._ev_fork, self._ev_join = torch.cuda.Event(), torch.cuda.Event()
+        self._ev_fork.record()          # torch creates the HIP event on its first record
+        self._ev_join.record()
+        if self.side is None:
+            self.side = torch.cuda.Stream(device=self.device)
+        return d
+
+    def native_start(self):
+        """Prime the native pipelined schedule: the first batch's unique into set 0."""
+        ctr.ctr_step_unique(self.native(), 0)
+        self._k = 0
+
+    def step_native(self, pipelined: bool = False, mark_begin=None, mark_end=None):
+        """One whole step in one native call (ctr_step_run); mark_begin/mark_end (optional
+        torch.cuda.Event) bracket the pooling kernel.  After it, the unique outputs of the
+        step's batch are the attributes (set k % 2 when pipelined)."""
+        assert self.pipelined or not pipelined, "the pipelined schedule needs two buffer sets"
+        d = self.native()
+        k = self._k
+        ctr.ctr_step_run(d, k, ctr.CTR_SCHEDULE_PIPELINED if pipelined else ctr.CTR_SCHEDULE_SERIAL,
+                         torch.cuda.current_stream(self.device), self.side, self._ev_fork,
+                         self._ev_join, mark_begin, mark_end)
+        self._use_set((k & 1) if pipelined else 0)
+        self._k = k + 1
+
+    def capture_native(self, steps: int, pipelined: bool, marks=None):
+        """Record `steps` consecutive native steps (k = 0 .. steps-1; even for the pipelined
+        schedule, whose set 0 must be primed before each replay sequence) into one HIP graph.
+        marks: optional list of 2*steps timing events around each step's pooling kernel, left
+        timed by every replay."""
+        assert not pipelined or (self.pipelined and steps % 2 == 0)
+        d = self.native()
+        sched = ctr.CTR_SCHEDULE_PIPELINED if pipelined else ctr.CTR_SCHEDULE_SERIAL
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            cap = torch.cuda.current_stream(self.device)
+            for i in range(steps):
+                m0 = marks[2 * i] if marks else None
+                m1 = marks[2 * i + 1] if marks else None
+                ctr.ctr_step_run(d, i, sched, cap, self.side, self._ev_fork, self._ev_join, m0, m1)
+        self._use_set(0)
+        return g
+
     def capture(self, names=None, steps: int = 1):
         """Record `steps` repetitions of the named stages (default: the whole step) into one
         HIP graph; replay with .replay().  The step allocates nothing, so the graph holds

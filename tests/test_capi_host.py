@@ -154,3 +154,43 @@ def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
     monkeypatch.setattr(ctr, "_lib", None)
     with pytest.raises(RuntimeError):
         ctr.load()
+
+
+def test_step_struct_layout_matches_header(tmp_path):
+    """The binding's CtrStep has the size and field offsets of ctr_step_t (checked with the
+    host C compiler against include/ctr.h)."""
+    fields = [f for f, _ in ctr.CtrStep._fields_]
+    src = tmp_path / "layout.c"
+    src.write_text('#include <stdio.h>\n#include <stddef.h>\n#include "%s"\nint main(void){'
+                   'printf("size %%zu\\n", sizeof(ctr_step_t));%s return 0;}\n'
+                   % (HEADER, "".join('printf("%s %%zu\\n", offsetof(ctr_step_t, %s));' % (f, f)
+                                      for f in fields)))
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-std=c11", "-o", str(exe), str(src)], check=True)
+    got = dict(line.split() for line in subprocess.run([str(exe)], capture_output=True,
+                                                       text=True, check=True).stdout.splitlines())
+    assert int(got["size"]) == ctypes.sizeof(ctr.CtrStep)
+    for f in fields:
+        assert getattr(ctr.CtrStep, f).offset == int(got[f]), f
+
+
+def test_step_run_bad_args():
+    lib = _lib()
+    d = ctr.CtrStep()
+    assert lib.ctr_step_run(None, 0, 0, None, None, None, None, None, None) == \
+        ctr.CTR_ERR_INVALID_ARGUMENT
+    d.kind = 7
+    assert lib.ctr_step_run(ctypes.byref(d), 0, 0, None, None, None, None, None, None) == \
+        ctr.CTR_ERR_INVALID_ARGUMENT
+    d.kind = ctr.CTR_STEP_POOLED_INTERACTION
+    # pipelined without a side stream; side stream without events; negative step; bad schedule
+    assert lib.ctr_step_run(ctypes.byref(d), 0, ctr.CTR_SCHEDULE_PIPELINED, None, None, None,
+                            None, None, None) == ctr.CTR_ERR_INVALID_ARGUMENT
+    assert lib.ctr_step_run(ctypes.byref(d), 0, 0, None, FAKE, None, None, None, None) == \
+        ctr.CTR_ERR_INVALID_ARGUMENT
+    assert lib.ctr_step_run(ctypes.byref(d), -1, 0, None, None, None, None, None, None) == \
+        ctr.CTR_ERR_INVALID_ARGUMENT
+    assert lib.ctr_step_run(ctypes.byref(d), 0, 5, None, None, None, None, None, None) == \
+        ctr.CTR_ERR_INVALID_ARGUMENT
+    assert lib.ctr_step_unique(ctypes.byref(d), 2, None) == ctr.CTR_ERR_INVALID_ARGUMENT
+

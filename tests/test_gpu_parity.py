@@ -556,3 +556,78 @@ def test_pipelined_schedule_matches_serial(name, graphs):
         else:
             np.testing.assert_array_equal(host(fa.out), host(fb.out))
         assert torch.equal(fa.table, fb.table)
+
+
+@pytest.mark.parametrize("pipelined", [False, True])
+@pytest.mark.parametrize("name", ["small_b256", "criteo_b128", "tensornet_b512"])
+def test_native_step_matches_python_steps(name, pipelined):
+    """ctr_step_run (the whole step in one native call) leaves the table, the forward outputs
+    and the row gradients bit-identical to the same schedule driven call by call."""
+    w = {"small_b256": lambda: workloads.small(batch=256),
+         "criteo_b128": lambda: workloads.criteo(batch=128),
+         "tensornet_b512": lambda: workloads.tensornet(batch=512, slots=100,
+                                                       table_rows=500_000)}[name]()
+    say("native step", name, "pipelined" if pipelined else "serial")
+    fa = FrontEnd(w, DEV, keep_grads=True, pipelined=pipelined)
+    fb = FrontEnd(w, DEV, keep_grads=True, pipelined=pipelined)
+    if pipelined:
+        fa.pipeline_start()
+        fb.native_start()
+    for _ in range(3):
+        if pipelined:
+            fa.step_pipelined(fork_after="embbag_fwd")
+        else:
+            fa.step()
+        fb.step_native(pipelined=pipelined)
+        torch.cuda.synchronize()
+        U = int(host(fa.num_unique)[0])
+        assert U == int(host(fb.num_unique)[0])
+        np.testing.assert_array_equal(host(fa.uniq)[:U], host(fb.uniq)[:U])
+        np.testing.assert_array_equal(host(fa.sorted_src), host(fb.sorted_src))
+        np.testing.assert_array_equal(host(fa.row_grads)[:U], host(fb.row_grads)[:U])
+        if w.interaction:
+            np.testing.assert_array_equal(host(fa.R), host(fb.R))
+            np.testing.assert_array_equal(host(fa.dZ), host(fb.dZ))
+        else:
+            np.testing.assert_array_equal(host(fa.out), host(fb.out))
+        assert torch.equal(fa.table, fb.table)
+
+
+@pytest.mark.parametrize("pipelined", [False, True])
+@pytest.mark.parametrize("name", ["small_b256", "tensornet_b512"])
+def test_native_step_graph_matches_eager(name, pipelined):
+    """Native steps captured as one HIP graph (the timing marks as event-record nodes) and
+    replayed twice, with unrelated eager work and synchronizations in between, leave the same
+    table, outputs and row gradients as the same steps run eagerly; every mark pair comes
+    back timed."""
+    w = (workloads.small(batch=256) if name == "small_b256"
+         else workloads.tensornet(batch=512, slots=100, table_rows=500_000))
+    say("native graph", name, "pipelined" if pipelined else "serial")
+    K = 4
+    fa = FrontEnd(w, DEV, keep_grads=True, pipelined=True)
+    fb = FrontEnd(w, DEV, keep_grads=True, pipelined=True)
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(2 * K)]
+    for m in marks:
+        m.record()
+    torch.cuda.synchronize()
+    g = fb.capture_native(K, pipelined, marks)
+    if pipelined:
+        fa.native_start()
+    junk = torch.randn(1 << 20, device=DEV)
+    for _ in range(2):
+        if pipelined:
+            fb.native_start()
+        for _ in range(K):
+            fa.step_native(pipelined)
+        g.replay()
+        junk.mul_(1.0001).add_(1.0)
+        torch.cuda.synchronize()
+        assert torch.equal(fa.table, fb.table)
+        U = int(host(fa.num_unique)[0])
+        np.testing.assert_array_equal(host(fa.row_grads)[:U], host(fb.row_grads)[:U])
+        if w.interaction:
+            np.testing.assert_array_equal(host(fa.R), host(fb.R))
+        else:
+            np.testing.assert_array_equal(host(fa.out), host(fb.out))
+        for i in range(K):
+            assert marks[2 * i].elapsed_time(marks[2 * i + 1]) > 0.0
