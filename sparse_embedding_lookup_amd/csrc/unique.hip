@@ -10,7 +10,8 @@
 //             occurrence comes from a shuffle binary search over the 64 bag ends, so the
 //             table and the bag are known without a search over all offsets)
 //   upsweep   each block counts digits of its contiguous range (wave-aggregated counts)
-//   scan      one block per digit scans that digit's per-block counts
+//   scan      one block per digit scans that digit's per-block counts (with few blocks the
+//             downsweep sums the digit's row of counts itself, with 16-byte loads)
 //   downsweep each block ranks its tiles stably with wave64 ballot "multisplit" (one
 //             ballot per digit bit gives the mask of lanes holding the same digit), stages
 //             the tile in LDS in digit order and writes it out in runs per digit.
@@ -29,6 +30,7 @@ constexpr int kMaxBits = 8;                   // widest digit (wider digits scat
 constexpr int kBuckets = 1 << kMaxBits;
 constexpr int kMaxBlocks = 1024;              // radix blocks (ranges) per pass
 constexpr int kFinTile = 2048;                // positions per finalize block
+constexpr int kFusedScanBlocks = 64;          // up to this many blocks, no scan kernel
 
 __device__ __forceinline__ uint64_t lanemask_lt() {
   const int lane = threadIdx.x & 63;
@@ -133,11 +135,12 @@ __global__ __launch_bounds__(kThreads) void form_keys_flat_kernel(const void* __
 }
 
 // --------------------------------------------------------------------------- upsweep
-// Digit counts of each block's contiguous range; hist is block-major: hist[block][digit].
+// Digit counts of each block's contiguous range; hist is digit-major: hist[digit * ld + block]
+// (ld = block count rounded up to 4), so one digit's counts over the blocks are contiguous.
 template <typename K>
 __global__ __launch_bounds__(kThreads) void radix_upsweep_kernel(
     const K* __restrict__ keys, int64_t n, int shift, int nbits, int64_t per_block,
-    uint32_t* __restrict__ hist) {
+    uint32_t* __restrict__ hist, int ld) {
   __shared__ uint32_t cnt[4][kBuckets];
   const int wave = threadIdx.x >> 6;
   for (int i = threadIdx.x; i < 4 * kBuckets; i += kThreads) (&cnt[0][0])[i] = 0;
@@ -156,14 +159,14 @@ __global__ __launch_bounds__(kThreads) void radix_upsweep_kernel(
   }
   __syncthreads();
   const int d = threadIdx.x;
-  hist[(int64_t)blockIdx.x * kBuckets + d] = cnt[0][d] + cnt[1][d] + cnt[2][d] + cnt[3][d];
+  hist[(int64_t)d * ld + blockIdx.x] = cnt[0][d] + cnt[1][d] + cnt[2][d] + cnt[3][d];
 }
 
 // --------------------------------------------------------------------------- scan
 // Many blocks: block d scans digit d's counts over the blocks (exclusive, in place) and
 // stores the digit total.  (With few blocks the downsweep does this itself.)
 __global__ __launch_bounds__(kThreads) void radix_scan_kernel(uint32_t* __restrict__ hist,
-                                                              int nblocks,
+                                                              int nblocks, int ld,
                                                               uint32_t* __restrict__ totals) {
   __shared__ uint32_t tmp[4];
   const int d = blockIdx.x;
@@ -173,14 +176,14 @@ __global__ __launch_bounds__(kThreads) void radix_scan_kernel(uint32_t* __restri
   uint32_t sum = 0;
   for (int j = 0; j < per; ++j) {
     const int k = b0 + j;
-    local[j] = k < nblocks ? hist[(int64_t)k * kBuckets + d] : 0u;
+    local[j] = k < nblocks ? hist[(int64_t)d * ld + k] : 0u;
     sum += local[j];
   }
   uint32_t total;
   uint32_t run = block_excl_scan_256(sum, tmp, &total);
   for (int j = 0; j < per; ++j) {
     const int k = b0 + j;
-    if (k < nblocks) hist[(int64_t)k * kBuckets + d] = run;
+    if (k < nblocks) hist[(int64_t)d * ld + k] = run;
     run += local[j];
   }
   if (threadIdx.x == 0) totals[d] = total;
@@ -208,7 +211,7 @@ __global__ __launch_bounds__(kThreads) void radix_downsweep_kernel(
     const uint32_t* __restrict__ bags_in, K* __restrict__ keys_out,
     uint32_t* __restrict__ vals_out, uint32_t* __restrict__ bags_out, int64_t n, int shift,
     int nbits, int64_t per_block, const uint32_t* __restrict__ hist,
-    const uint32_t* __restrict__ totals, int nblocks) {
+    const uint32_t* __restrict__ totals, int nblocks, int ld) {
   constexpr int kT = kThreads * ITEMS;
   __shared__ DownsweepSmem<K, ITEMS> sm;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -220,16 +223,27 @@ __global__ __launch_bounds__(kThreads) void radix_downsweep_kernel(
     const int d = threadIdx.x;
     uint32_t tot, before;
     if (FUSED) {
+      // digit d's counts over all blocks are one contiguous row: 16-byte loads, all issued
+      // before any is summed
       tot = 0;
       before = 0;
-      for (int g = 0; g < nblocks; ++g) {
-        const uint32_t c = hist[(int64_t)g * kBuckets + d];
-        tot += c;
-        if (g < (int)blockIdx.x) before += c;
+      const uint4* row = reinterpret_cast<const uint4*>(hist + (int64_t)d * ld);
+      const int me = (int)blockIdx.x;
+#pragma unroll 8
+      for (int g4 = 0; g4 < ld / 4; ++g4) {
+        const uint4 v = row[g4];
+        const uint32_t c[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int g = 4 * g4 + j;
+          const uint32_t x = g < nblocks ? c[j] : 0u;
+          tot += x;
+          before += g < me ? x : 0u;
+        }
       }
     } else {
       tot = totals[d];
-      before = hist[(int64_t)blockIdx.x * kBuckets + d];
+      before = hist[(int64_t)d * ld + blockIdx.x];
     }
     uint32_t all;
     sm.run[d] = block_excl_scan_256(tot, sm.tmp, &all) + before;
@@ -517,12 +531,14 @@ void radix_pass(bool first, bool bags, const K* kin, const uint32_t* vin, const 
                 K* kout, uint32_t* vout, uint32_t* bout, int64_t n, int shift, int nbits,
                 int64_t per_block, uint32_t* hist, uint32_t* totals, int nblocks,
                 hipStream_t s) {
-  radix_upsweep_kernel<K><<<nblocks, kThreads, 0, s>>>(kin, n, shift, nbits, per_block, hist);
-  const bool fused = nblocks <= kThreads;
-  if (!fused) radix_scan_kernel<<<kBuckets, kThreads, 0, s>>>(hist, nblocks, totals);
+  const int ld = (nblocks + 3) & ~3;
+  radix_upsweep_kernel<K><<<nblocks, kThreads, 0, s>>>(kin, n, shift, nbits, per_block, hist,
+                                                       ld);
+  const bool fused = nblocks <= kFusedScanBlocks;
+  if (!fused) radix_scan_kernel<<<kBuckets, kThreads, 0, s>>>(hist, nblocks, ld, totals);
 #define CTR_DS(I, B, FU)                                                                   \
   radix_downsweep_kernel<K, ITEMS, I, B, FU><<<nblocks, kThreads, 0, s>>>(                 \
-      kin, vin, bin, kout, vout, bout, n, shift, nbits, per_block, hist, totals, nblocks)
+      kin, vin, bin, kout, vout, bout, n, shift, nbits, per_block, hist, totals, nblocks, ld)
 #define CTR_DS2(I, B) \
   if (fused) CTR_DS(I, B, true); else CTR_DS(I, B, false)
   if (first) {
