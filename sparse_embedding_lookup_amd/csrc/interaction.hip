@@ -126,6 +126,144 @@ __global__ __launch_bounds__(kThreads) void interaction_bwd_f32_kernel(
   }
 }
 
+// ------------------------------------------------------------------------- fp32, lanes
+// For F <= FMAX and dim = 4L (L a power of two, at most 64): a sample is L lanes, lane l
+// holds columns 4l..4l+3 of all F vectors in registers (one 16-byte load each, all issued
+// at once), so a one-wave block serves 64/L samples and a batch of B samples launches
+// B*L/64 blocks.
+constexpr int kLaneThreads = 64;
+
+// Forward: R[b, 4l..] = z_0 slice; each pair's partial dot over the lane's 4 columns goes to
+// LDS (dynamic: samples x P x (L + 1) floats), and after one barrier lane l sums pairs
+// l, l + L, ... over the sample's L partials.  For FMAX = 32 (up to 496 pairs) the partials
+// are summed with xor shuffles instead.
+template <int FMAX, int L>
+__global__ __launch_bounds__(kLaneThreads) void interaction_fwd_lanes_kernel(
+    const float* __restrict__ Z, int64_t batch, int F, float* __restrict__ R, int64_t r_stride) {
+  constexpr int kDim = 4 * L;
+  constexpr bool kLds = FMAX <= 16;
+  extern __shared__ float part[];              // [64 / L][P][L + 1] when kLds
+  const int P = F * (F - 1) / 2;
+  const int lane = threadIdx.x % L;
+  const int64_t b = (int64_t)blockIdx.x * (kLaneThreads / L) + threadIdx.x / L;
+  const bool ok = b < batch;
+  const float* zb = Z + (ok ? b : 0) * (int64_t)F * kDim + 4 * lane;
+  float4 z[FMAX];
+#pragma unroll
+  for (int j = 0; j < FMAX; ++j)
+    z[j] = j < F ? *reinterpret_cast<const float4*>(zb + j * kDim) : make_float4(0.f, 0.f, 0.f, 0.f);
+  float* rb = R + (ok ? b : 0) * r_stride;
+  if (ok) {                                  // r_stride need not keep 16-byte alignment
+    rb[4 * lane] = z[0].x;
+    rb[4 * lane + 1] = z[0].y;
+    rb[4 * lane + 2] = z[0].z;
+    rb[4 * lane + 3] = z[0].w;
+  }
+  const int sl = threadIdx.x / L;
+  float* ps = part + (int64_t)sl * P * (L + 1);
+  int p = 0;
+#pragma unroll
+  for (int i = 1; i < FMAX; ++i) {
+#pragma unroll
+    for (int j = 0; j < i; ++j, ++p) {
+      if (i < F) {
+        float v = z[i].x * z[j].x;
+        v = __builtin_fmaf(z[i].y, z[j].y, v);
+        v = __builtin_fmaf(z[i].z, z[j].z, v);
+        v = __builtin_fmaf(z[i].w, z[j].w, v);
+        if constexpr (kLds) {
+          ps[p * (L + 1) + lane] = v;
+        } else {
+#pragma unroll
+          for (int o = L / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, L);
+          if (ok && lane == p % L) rb[kDim + p] = v;
+        }
+      }
+    }
+  }
+  if constexpr (kLds) {
+    __syncthreads();
+    for (int q = lane; q < P; q += L) {
+      const float* row = ps + q * (L + 1);
+      float v = 0.f;
+#pragma unroll
+      for (int l = 0; l < L; ++l) v += row[l];
+      if (ok) rb[kDim + q] = v;
+    }
+  }
+}
+
+// Backward: dZ_i = sum_{j != i} dP(i, j) z_j (+ dR_dense for i = 0), one output slice at a
+// time; the sample's pair gradients are staged in LDS and read as broadcasts.
+template <int FMAX, int L>
+__global__ __launch_bounds__(kLaneThreads) void interaction_bwd_lanes_kernel(
+    const float* __restrict__ Z, const float* __restrict__ dR, int64_t dr_stride, int64_t batch,
+    int F, float* __restrict__ dZ) {
+  constexpr int kDim = 4 * L;
+  constexpr int kS = kLaneThreads / L;                     // samples per block
+  constexpr int kPmax = FMAX * (FMAX - 1) / 2;
+  __shared__ float dp[kS][kPmax];
+  const int P = F * (F - 1) / 2;
+  const int64_t b0 = (int64_t)blockIdx.x * kS;
+  for (int q = threadIdx.x; q < kS * P; q += kLaneThreads) {
+    const int s = q / P, r = q - s * P;
+    dp[s][r] = b0 + s < batch ? dR[(b0 + s) * dr_stride + kDim + r] : 0.f;
+  }
+  const int lane = threadIdx.x % L, sl = threadIdx.x / L;
+  const int64_t b = b0 + sl;
+  const bool ok = b < batch;
+  const float* zb = Z + (ok ? b : 0) * (int64_t)F * kDim + 4 * lane;
+  float4 z[FMAX];
+#pragma unroll
+  for (int j = 0; j < FMAX; ++j)
+    z[j] = j < F ? *reinterpret_cast<const float4*>(zb + j * kDim) : make_float4(0.f, 0.f, 0.f, 0.f);
+  const float* drb = dR + (ok ? b : 0) * dr_stride + 4 * lane;     // any stride alignment
+  const float4 dense = make_float4(drb[0], drb[1], drb[2], drb[3]);
+  __syncthreads();
+  float* db = dZ + (ok ? b : 0) * (int64_t)F * kDim + 4 * lane;
+#pragma unroll
+  for (int i = 0; i < FMAX; ++i) {
+    if (i < F) {
+      float4 acc = i == 0 ? dense : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+      for (int j = 0; j < FMAX; ++j) {
+        if (j != i && j < F) {
+          const float g = dp[sl][i > j ? i * (i - 1) / 2 + j : j * (j - 1) / 2 + i];
+          acc.x = __builtin_fmaf(g, z[j].x, acc.x);
+          acc.y = __builtin_fmaf(g, z[j].y, acc.y);
+          acc.z = __builtin_fmaf(g, z[j].z, acc.z);
+          acc.w = __builtin_fmaf(g, z[j].w, acc.w);
+        }
+      }
+      if (ok) *reinterpret_cast<float4*>(db + i * kDim) = acc;
+    }
+  }
+}
+
+// Dispatch of the lane kernels: FMAX in {8, 16, 32}, L in {1, ..., 64}; false if the shape
+// is not covered (then the LDS-staged kernels serve it).
+#define CTR_LANES_L(FM, ...)                                                  \
+  switch (L_) {                                                             \
+    case 1: { constexpr int FMAX = FM, L = 1; __VA_ARGS__; } break;          \
+    case 2: { constexpr int FMAX = FM, L = 2; __VA_ARGS__; } break;          \
+    case 4: { constexpr int FMAX = FM, L = 4; __VA_ARGS__; } break;          \
+    case 8: { constexpr int FMAX = FM, L = 8; __VA_ARGS__; } break;          \
+    case 16: { constexpr int FMAX = FM, L = 16; __VA_ARGS__; } break;        \
+    case 32: { constexpr int FMAX = FM, L = 32; __VA_ARGS__; } break;        \
+    default: { constexpr int FMAX = FM, L = 64; __VA_ARGS__; } break;        \
+  }
+#define CTR_LANES(F_, L_, ...)                                               \
+  do {                                                                      \
+    if ((F_) <= 8) { CTR_LANES_L(8, __VA_ARGS__) }                           \
+    else if ((F_) <= 16) { CTR_LANES_L(16, __VA_ARGS__) }                    \
+    else { CTR_LANES_L(32, __VA_ARGS__) }                                    \
+  } while (0)
+
+bool lanes_shape(int F, int dim) {
+  const int L = dim / 4;
+  return F <= 32 && dim % 4 == 0 && L >= 1 && L <= 64 && (L & (L - 1)) == 0;
+}
+
 // ------------------------------------------------------------------------- bf16 forward
 // Operand fragment of row-block I, k-step s: lane holds row 32*I + rl, columns
 // 16*s + 8*kg .. +8 of Z[b], rounded to bf16 (rows >= F are zero).
@@ -328,6 +466,15 @@ hipError_t launch_interaction_fwd(const float* Z, int64_t batch, int F, int dim,
                                   float* R, int64_t r_stride, hipStream_t s) {
   if (batch == 0) return hipSuccess;
   if (!bf16) {
+    if (lanes_shape(F, dim)) {
+      const int L_ = dim / 4;
+      const int64_t blocks = (batch * L_ + kLaneThreads - 1) / kLaneThreads;
+      const size_t lds = F <= 16 ? (size_t)(kLaneThreads / L_) * (F * (F - 1) / 2) * (L_ + 1) *
+                                       sizeof(float) : 0;
+      CTR_LANES(F, L_, interaction_fwd_lanes_kernel<FMAX, L><<<(unsigned)blocks, kLaneThreads, lds, s>>>(
+                           Z, batch, F, R, r_stride));
+      return hipGetLastError();
+    }
     const int spb = f32_spb(batch, F, dim, false);
     const size_t lds = (size_t)spb * F * (dim + 1) * sizeof(float);
     const int64_t blocks = (batch + spb - 1) / spb;
@@ -354,6 +501,13 @@ hipError_t launch_interaction_bwd(const float* Z, const float* dR, int64_t dr_st
   if (batch == 0) return hipSuccess;
   const int P = F * (F - 1) / 2;
   if (!bf16) {
+    if (lanes_shape(F, dim)) {
+      const int L_ = dim / 4;
+      const int64_t blocks = (batch * L_ + kLaneThreads - 1) / kLaneThreads;
+      CTR_LANES(F, L_, interaction_bwd_lanes_kernel<FMAX, L><<<(unsigned)blocks, kLaneThreads, 0, s>>>(
+                           Z, dR, dr_stride, batch, F, dZ));
+      return hipGetLastError();
+    }
     const int spb = f32_spb(batch, F, dim, true);
     const size_t lds = (size_t)spb * (F * (dim + 1) + P) * sizeof(float);
     const int64_t blocks = (batch + spb - 1) / spb;

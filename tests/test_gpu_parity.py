@@ -231,6 +231,9 @@ INTER_CASES = [
     ("f32", 128, 5, 16), ("f32", 2048, 9, 64), ("f32", 77, 2, 4), ("f32", 33, 27, 128),
     ("bf16", 100, 27, 128), ("bf16", 67, 65, 128), ("bf16", 40, 5, 16), ("bf16", 9, 2, 32),
     ("bf16", 13, 100, 64), ("f32", 5, 65, 128),
+    # fp32 lane kernels at their F / dim boundaries, and shapes left to the LDS kernels
+    ("f32", 50, 16, 32), ("f32", 45, 32, 256), ("f32", 19, 17, 48), ("f32", 64, 33, 16),
+    ("f32", 3, 8, 8),
 ]
 
 
