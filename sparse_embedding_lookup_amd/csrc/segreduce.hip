@@ -24,6 +24,7 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kPerSlot = 8;      // positions summed by one slot (more slots, fewer registers)
+constexpr int64_t kFoldBlocks = 256;   // a level this small may finish the tree in place
 
 __global__ __launch_bounds__(kThreads) void bag_of_kernel(const int64_t* __restrict__ offsets,
                                                           int64_t num_bags, int64_t nnz,
@@ -292,18 +293,19 @@ __device__ __forceinline__ void slot_prefetched(const L0Source& S, int64_t q0, i
   }
 }
 
-// One reduce-by-key level.  L0: entries are sorted positions of the occurrences (keys from
-// src, rows gathered from grad); otherwise entries are carries (keys may be -1 = empty).
+// One chunk of a reduce-by-key level.  L0: entries are sorted positions of the occurrences
+// (keys from src, rows gathered from grad); otherwise entries are carries (keys may be -1 =
+// empty).  The chunk's at most two carries go to out_keys / out_rows[2 * chunk + {0, 1}].
 template <bool L0, int G, int VPL, int MODE, typename Src>
-__global__ __launch_bounds__(kThreads) void segreduce_kernel(
-    Src S, int64_t n, int dim, int64_t capacity, float* __restrict__ row_grads, SgdTarget sgd,
-    int32_t* __restrict__ out_keys, float* __restrict__ out_rows) {
+__device__ __forceinline__ void reduce_chunk(
+    SegSmem<G, VPL>& sm, Src S, int64_t n, int64_t chunk_id, int dim, int64_t capacity,
+    float* __restrict__ row_grads, const SgdTarget& sgd, int32_t* __restrict__ out_keys,
+    float* __restrict__ out_rows) {
   constexpr int kSlots = kThreads / G;
   constexpr int kW = G * VPL * 4;              // floats per slot row in LDS
-  __shared__ SegSmem<G, VPL> sm;
   const int lane = threadIdx.x & (G - 1);
   const int slot = threadIdx.x / G;
-  const int64_t chunk0 = (int64_t)blockIdx.x * kSlots * kPerSlot;
+  const int64_t chunk0 = chunk_id * kSlots * kPerSlot;
   const int64_t q0 = chunk0 + (int64_t)slot * kPerSlot;
   const int64_t q1 = q0 + kPerSlot < n ? q0 + kPerSlot : n;
   const int64_t chunk1 = chunk0 + (int64_t)kSlots * kPerSlot < n ? chunk0 + (int64_t)kSlots * kPerSlot : n;
@@ -479,7 +481,7 @@ __global__ __launch_bounds__(kThreads) void segreduce_kernel(
   // Join the pieces of segments that cross slot edges.  The owner of a segment is the slot
   // where it starts (its "last" piece) or, for the segment that started before this chunk,
   // slot 0.  Walking right adds the next slots' "first" pieces until one does not continue.
-  const int64_t carry_base = 2 * (int64_t)blockIdx.x;
+  const int64_t carry_base = 2 * chunk_id;
   auto walk = [&](int32_t u, int start_slot, RowAcc<VPL>& acc) -> bool {
     int j = start_slot;
     while (j < kSlots) {
@@ -542,11 +544,48 @@ __global__ __launch_bounds__(kThreads) void segreduce_kernel(
   (void)kW;
 }
 
+// One reduce-by-key level, a chunk per block.  With `ticket`, the level is the last but one:
+// its carries fit one chunk, and the block that finishes last reduces them as the final
+// level (its writes published by a device-scope fence before the ticket; the finisher
+// fences again before it reads them), which saves a launch.  The L0 kernel, which always
+// precedes, zeroes the ticket.
+template <bool L0, int G, int VPL, int MODE, typename Src>
+__global__ __launch_bounds__(kThreads) void segreduce_kernel(
+    Src S, int64_t n, int dim, int64_t capacity, float* __restrict__ row_grads, SgdTarget sgd,
+    int32_t* __restrict__ out_keys, float* __restrict__ out_rows, uint32_t* __restrict__ ticket,
+    float* __restrict__ spare_rows) {
+  __shared__ SegSmem<G, VPL> sm;
+  __shared__ uint32_t finisher;
+  if constexpr (L0) {
+    if (ticket && blockIdx.x == 0 && threadIdx.x == 0) *ticket = 0u;
+  }
+  reduce_chunk<L0, G, VPL, MODE, Src>(sm, S, n, (int64_t)blockIdx.x, dim, capacity, row_grads,
+                                      sgd, out_keys, out_rows);
+  if constexpr (!L0) {
+    if (ticket) {
+      __syncthreads();
+      if (threadIdx.x == 0) {
+        __threadfence();
+        finisher = atomicAdd(ticket, 1u) == gridDim.x - 1 ? 1u : 0u;
+      }
+      __syncthreads();
+      if (finisher) {
+        __threadfence();
+        const LnSource fin{out_keys, out_rows, dim};
+        reduce_chunk<false, G, VPL, MODE, LnSource>(sm, fin, 2 * (int64_t)gridDim.x, 0, dim,
+                                                    capacity, row_grads, sgd, nullptr,
+                                                    spare_rows);
+      }
+    }
+  }
+}
+
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct BwdWs {
   int32_t* bag_of;
   int4* src;
+  uint32_t* ticket;        // finish-level ticket (zeroed by the L0 kernel)
   int32_t* ckeys[2];
   float* crows[2];
   size_t bytes;
@@ -570,6 +609,7 @@ BwdWs carve(void* base, int64_t n, int dim) {
   const int64_t c1 = 2 * ((n + chunk - 1) / chunk);   // carries out of level 0 (largest)
   w.bag_of = reinterpret_cast<int32_t*>(take(sizeof(int32_t) * (size_t)n));
   w.src = reinterpret_cast<int4*>(take(sizeof(int4) * (size_t)n));
+  w.ticket = reinterpret_cast<uint32_t*>(take(256));
   for (int k = 0; k < 2; ++k) {
     w.ckeys[k] = reinterpret_cast<int32_t*>(take(sizeof(int32_t) * (size_t)(c1 + 2)));
     w.crows[k] = reinterpret_cast<float*>(take(sizeof(float) * (size_t)(c1 + 2) * dim));
@@ -610,15 +650,19 @@ static void segreduce_levels(const L0Source& s0, int64_t nnz, int dim, float* ro
     int64_t blocks = (len + chunk - 1) / chunk;
     int cur = 0;
     segreduce_kernel<true, G, VPL, MODE, L0Source><<<(unsigned)blocks, kThreads, 0, s>>>(
-        s0, len, dim, nnz, row_grads, sgd, blocks > 1 ? w.ckeys[cur] : nullptr, w.crows[cur]);
+        s0, len, dim, nnz, row_grads, sgd, blocks > 1 ? w.ckeys[cur] : nullptr, w.crows[cur],
+        w.ticket, nullptr);
     while (blocks > 1) {
       len = 2 * blocks;
       blocks = (len + chunk - 1) / chunk;
       LnSource sn{w.ckeys[cur], w.crows[cur], dim};
+      // a level whose carries fit one chunk finishes the tree itself
+      const bool fold = blocks > 1 && 2 * blocks <= chunk && blocks <= kFoldBlocks;
       segreduce_kernel<false, G, VPL, MODE, LnSource><<<(unsigned)blocks, kThreads, 0, s>>>(
           sn, len, dim, nnz, row_grads, sgd, blocks > 1 ? w.ckeys[cur ^ 1] : nullptr,
-          w.crows[cur ^ 1]);
+          w.crows[cur ^ 1], fold ? w.ticket : nullptr, w.crows[cur]);
       cur ^= 1;
+      if (fold) break;
     }
   });
 }
