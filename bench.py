@@ -13,9 +13,9 @@ HIP events on its stream inside the timed region) and the CPU oracle timed on a 
 sample of the same workload.
 
 Schedule (default "pipelined"): training consumes a stream of batches, and the ID dedup of
-batch k+1 needs only that batch's IDs, so it runs on a second stream during step k (forked
-right after the dominant kernel, which thus runs alone) into a second set of output
-buffers; each timed step still launches every call of the path once.  "serial" dedups each
+batch k+1 needs only that batch's IDs, so it runs on a second stream during step k into a
+second set of output buffers (forked when the step starts; --fork after-pooling forks it
+right after the pooling kernel); each timed step still launches every call of the path once.  "serial" dedups each
 batch inside its own step; --compare-serial adds that schedule's ms per step to a pipelined
 run.
 
@@ -190,6 +190,9 @@ def main():
     ap.add_argument("--schedule", default="pipelined", choices=["pipelined", "serial"],
                     help="pipelined: batch k+1's ID dedup runs during step k (double-buffered "
                          "outputs); serial: every step dedups its own batch first")
+    ap.add_argument("--fork", default="early", choices=["early", "after-pooling"],
+                    help="pipelined schedule: fork the next batch's unique when the step "
+                         "starts, or right after the pooling kernel (native and graph launch)")
     ap.add_argument("--compare-serial", action="store_true",
                     help="after a pipelined run, also time K serial steps (ms_per_step_serial)")
     args = ap.parse_args()
@@ -209,6 +212,7 @@ def main():
     graph = args.launch == "graph"
     native = args.launch in ("native", "graph")
     pipelined = args.schedule == "pipelined"
+    early = args.fork == "early"
     if graph and pipelined and args.steps % 2:
         args.steps += 1                  # a pipelined graph holds whole pairs of steps
     fe = FrontEnd(w, "cuda", pipelined=pipelined)
@@ -232,7 +236,7 @@ def main():
             if pipelined:
                 fe.native_start()
             for _ in range(args.warmup):
-                fe.step_native(pipelined)
+                fe.step_native(pipelined, early=early)
         elif pipelined:
             fe.pipeline_start()
             for _ in range(args.warmup):
@@ -290,7 +294,8 @@ def main():
         e.record()                       # torch creates the HIP event on its first record
     torch.cuda.synchronize()
     if graph:
-        g_steps = fe.capture_native(K, pipelined, [e for pair in zip(dev0, dev1) for e in pair])
+        g_steps = fe.capture_native(K, pipelined, [e for pair in zip(dev0, dev1) for e in pair],
+                                    early=early)
         if pipelined:
             fe.native_start()
         g_steps.replay()                 # warm replay
@@ -305,7 +310,7 @@ def main():
     else:
         if native:
             def one_step(k):
-                fe.step_native(pipelined, dev0[k], dev1[k])
+                fe.step_native(pipelined, dev0[k], dev1[k], early=early)
         else:
             def mark(name, fn):
                 if name == dominant:
@@ -367,8 +372,10 @@ def main():
                    "native: one ctr_step_run call enqueues the whole step" if native else
                    "eager up to the dominant kernel, then captured graphs (the next batch's "
                    "unique on a side stream; the rest of the step)" if pipelined else "eager"),
-        "schedule": ("pipelined: batch k+1's ID dedup runs during step k on a second stream "
-                     "(double-buffered outputs); every call runs once per step"
+        "schedule": (("pipelined: batch k+1's ID dedup runs during step k on a second stream "
+                      "(double-buffered outputs), forked %s; every call runs once per step"
+                      % ("when the step starts" if early and native else
+                         "after the pooling kernel"))
                      if pipelined else "serial: each step dedups its own batch"),
         "ms_per_step_serial": ms_serial if pipelined else ms_step,   # null unless compared
         "data": "synthetic (seeded; tables from the counter-based fill)",

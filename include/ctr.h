@@ -246,7 +246,7 @@ int32_t ctr_validate_csr(const void* indices, int32_t index_type, int64_t nnz,
  * (fp32 [nnz, dim]) is optional.
  */
 enum { CTR_STEP_POOLED_INTERACTION = 0, CTR_STEP_BATCH_MATRIX = 1 };
-enum { CTR_SCHEDULE_SERIAL = 0, CTR_SCHEDULE_PIPELINED = 1 };
+enum { CTR_SCHEDULE_SERIAL = 0, CTR_SCHEDULE_PIPELINED = 1, CTR_SCHEDULE_PIPELINED_EARLY = 2 };
 
 typedef struct {
   int32_t kind;
@@ -294,6 +294,8 @@ typedef struct {
  *                           next batch's unique is forked to side_stream into the other set,
  *                           and the step joins it before returning control of set k % 2.
  *                           (With one repeated batch, the next batch is the same IDs.)
+ *   CTR_SCHEDULE_PIPELINED_EARLY  the same, with the next batch's unique forked when the
+ *                           step starts, so that it also runs beside the pooling kernel.
  * fork_event / join_event: caller-created events (required with a side stream); mark_begin /
  * mark_end: optional events recorded on main_stream right before and after the pooling
  * kernel.  Under stream capture (graph building) the marks become event-record nodes of the

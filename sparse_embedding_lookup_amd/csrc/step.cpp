@@ -133,11 +133,12 @@ int32_t ctr_step_run(const ctr_step_t* d, int64_t k, int32_t schedule, void* mai
   if (d->kind != CTR_STEP_POOLED_INTERACTION && d->kind != CTR_STEP_BATCH_MATRIX)
     return invalid("unknown step kind");
   if (k < 0) return invalid("step index k < 0");
-  if (schedule != CTR_SCHEDULE_SERIAL && schedule != CTR_SCHEDULE_PIPELINED)
+  if (schedule != CTR_SCHEDULE_SERIAL && schedule != CTR_SCHEDULE_PIPELINED &&
+      schedule != CTR_SCHEDULE_PIPELINED_EARLY)
     return invalid("unknown schedule");
   if (side_stream && (!fork_event || !join_event))
     return invalid("a side stream needs fork and join events");
-  if (schedule == CTR_SCHEDULE_PIPELINED && !side_stream)
+  if (schedule != CTR_SCHEDULE_SERIAL && !side_stream)
     return invalid("the pipelined schedule needs a side stream");
   hipStream_t s = static_cast<hipStream_t>(main_stream);
   hipStream_t side = static_cast<hipStream_t>(side_stream);
@@ -159,13 +160,15 @@ int32_t ctr_step_run(const ctr_step_t* d, int64_t k, int32_t schedule, void* mai
   }
   // pipelined: batch k uses set k % 2 (filled during step k-1, or by ctr_step_unique before
   // the first step); batch k+1's unique fills the other set on the side stream, forked after
-  // the pooling kernel and joined before the step ends
+  // the pooling kernel (or when the step starts) and joined before the step ends
   const int cur = (int)(k & 1), nxt = cur ^ 1;
-  CTR_TRY(forward_part(d, cur, s, mark_begin, mark_end));
+  const bool early = schedule == CTR_SCHEDULE_PIPELINED_EARLY;
+  if (!early) CTR_TRY(forward_part(d, cur, s, mark_begin, mark_end));
   CTR_TRY(record(fork_event, s));
   CTR_TRY(wait(side, fork_event));
   CTR_TRY(unique_into(d, nxt, side));
   CTR_TRY(record(join_event, side));
+  if (early) CTR_TRY(forward_part(d, cur, s, mark_begin, mark_end));
   CTR_TRY(backward_part(d, cur, s, false, join_event));
   return wait(s, join_event);
 }

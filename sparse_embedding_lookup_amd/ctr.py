@@ -28,7 +28,7 @@ EXPORTED = [
 ]
 
 CTR_STEP_POOLED_INTERACTION, CTR_STEP_BATCH_MATRIX = 0, 1
-CTR_SCHEDULE_SERIAL, CTR_SCHEDULE_PIPELINED = 0, 1
+CTR_SCHEDULE_SERIAL, CTR_SCHEDULE_PIPELINED, CTR_SCHEDULE_PIPELINED_EARLY = 0, 1, 2
 
 
 class CtrStep(ctypes.Structure):
