@@ -14,8 +14,11 @@ sample of the same workload.
 
 Schedule (default "pipelined"): training consumes a stream of batches, and the ID dedup of
 batch k+1 needs only that batch's IDs, so it runs on a second stream during step k into a
-second set of output buffers (forked when the step starts; --fork after-pooling forks it
-right after the pooling kernel); each timed step still launches every call of the path once.  "serial" dedups each
+second set of output buffers; each timed step still launches every call of the path once.
+--pipeline overlap (default) waits for a batch's dedup only before that batch's backward, and
+lets the dedup of batch k+2 start once the backward of batch k has released its buffers, so
+consecutive steps overlap; early / after-pooling fork the dedup when the step starts / after
+the pooling kernel and join it at the step's end.  "serial" dedups each
 batch inside its own step; --compare-serial adds that schedule's ms per step to a pipelined
 run.
 
@@ -190,9 +193,12 @@ def main():
     ap.add_argument("--schedule", default="pipelined", choices=["pipelined", "serial"],
                     help="pipelined: batch k+1's ID dedup runs during step k (double-buffered "
                          "outputs); serial: every step dedups its own batch first")
-    ap.add_argument("--fork", default="early", choices=["early", "after-pooling"],
-                    help="pipelined schedule: fork the next batch's unique when the step "
-                         "starts, or right after the pooling kernel (native and graph launch)")
+    ap.add_argument("--pipeline", default="overlap",
+                    choices=["overlap", "early", "after-pooling"],
+                    help="pipelined schedule of the native step: overlap (each step waits for "
+                         "its batch's unique only before its backward; steps overlap), early "
+                         "(the next batch's unique forked at the step start, joined at its "
+                         "end) or after-pooling (forked after the pooling kernel)")
     ap.add_argument("--compare-serial", action="store_true",
                     help="after a pipelined run, also time K serial steps (ms_per_step_serial)")
     args = ap.parse_args()
@@ -212,7 +218,7 @@ def main():
     graph = args.launch == "graph"
     native = args.launch in ("native", "graph")
     pipelined = args.schedule == "pipelined"
-    early = args.fork == "early"
+    sched = args.pipeline if pipelined else "serial"
     if graph and pipelined and args.steps % 2:
         args.steps += 1                  # a pipelined graph holds whole pairs of steps
     fe = FrontEnd(w, "cuda", pipelined=pipelined)
@@ -236,7 +242,7 @@ def main():
             if pipelined:
                 fe.native_start()
             for _ in range(args.warmup):
-                fe.step_native(pipelined, early=early)
+                fe.step_native(sched)
         elif pipelined:
             fe.pipeline_start()
             for _ in range(args.warmup):
@@ -294,8 +300,7 @@ def main():
         e.record()                       # torch creates the HIP event on its first record
     torch.cuda.synchronize()
     if graph:
-        g_steps = fe.capture_native(K, pipelined, [e for pair in zip(dev0, dev1) for e in pair],
-                                    early=early)
+        g_steps = fe.capture_native(K, sched, [e for pair in zip(dev0, dev1) for e in pair])
         if pipelined:
             fe.native_start()
         g_steps.replay()                 # warm replay
@@ -310,7 +315,7 @@ def main():
     else:
         if native:
             def one_step(k):
-                fe.step_native(pipelined, dev0[k], dev1[k], early=early)
+                fe.step_native(sched, dev0[k], dev1[k])
         else:
             def mark(name, fn):
                 if name == dominant:
@@ -340,10 +345,10 @@ def main():
     if pipelined and args.compare_serial:
         # the same K steps with each batch's unique inside its own step, for comparison
         if graph:
-            g_ser = fe.capture_native(K, False)
+            g_ser = fe.capture_native(K, "serial")
             serial_steps = [g_ser.replay]
         else:
-            serial_steps = [(lambda: fe.step_native(False)) if native else fe.step] * K
+            serial_steps = [(lambda: fe.step_native("serial")) if native else fe.step] * K
         for f in serial_steps[:2]:
             f()
         torch.cuda.synchronize()
@@ -373,9 +378,13 @@ def main():
                    "eager up to the dominant kernel, then captured graphs (the next batch's "
                    "unique on a side stream; the rest of the step)" if pipelined else "eager"),
         "schedule": (("pipelined: batch k+1's ID dedup runs during step k on a second stream "
-                      "(double-buffered outputs), forked %s; every call runs once per step"
-                      % ("when the step starts" if early and native else
-                         "after the pooling kernel"))
+                      "(double-buffered outputs)%s; every call runs once per step"
+                      % ({"overlap": "; each backward waits only for its own batch's dedup, "
+                                     "so consecutive steps overlap",
+                          "early": ", forked when the step starts, joined at its end",
+                          "after-pooling": ", forked after the pooling kernel, joined at "
+                                           "the step's end"}[args.pipeline] if native
+                         else ", forked after the pooling kernel"))
                      if pipelined else "serial: each step dedups its own batch"),
         "ms_per_step_serial": ms_serial if pipelined else ms_step,   # null unless compared
         "data": "synthetic (seeded; tables from the counter-based fill)",

@@ -246,7 +246,12 @@ int32_t ctr_validate_csr(const void* indices, int32_t index_type, int64_t nnz,
  * (fp32 [nnz, dim]) is optional.
  */
 enum { CTR_STEP_POOLED_INTERACTION = 0, CTR_STEP_BATCH_MATRIX = 1 };
-enum { CTR_SCHEDULE_SERIAL = 0, CTR_SCHEDULE_PIPELINED = 1, CTR_SCHEDULE_PIPELINED_EARLY = 2 };
+enum {
+  CTR_SCHEDULE_SERIAL = 0,
+  CTR_SCHEDULE_PIPELINED = 1,
+  CTR_SCHEDULE_PIPELINED_EARLY = 2,
+  CTR_SCHEDULE_PIPELINED_OVERLAP = 3
+};
 
 typedef struct {
   int32_t kind;
@@ -296,6 +301,14 @@ typedef struct {
  *                           (With one repeated batch, the next batch is the same IDs.)
  *   CTR_SCHEDULE_PIPELINED_EARLY  the same, with the next batch's unique forked when the
  *                           step starts, so that it also runs beside the pooling kernel.
+ *   CTR_SCHEDULE_PIPELINED_OVERLAP  no join at the step's end: the backward of step k waits
+ *                           for batch k's unique (join_event, recorded by step k-1) and batch
+ *                           k+1's unique waits for the backward of step k-1 (fork_event,
+ *                           recorded at the end of each step), so consecutive steps overlap.
+ *                           Step 0 (k == 0) waits on nothing earlier; before reading results,
+ *                           or at the end of a stream capture, make main_stream wait for
+ *                           side_stream.  fork_event and join_event carry state between calls:
+ *                           record nothing else into them.
  * fork_event / join_event: caller-created events (required with a side stream); mark_begin /
  * mark_end: optional events recorded on main_stream right before and after the pooling
  * kernel.  Under stream capture (graph building) the marks become event-record nodes of the

@@ -90,18 +90,19 @@ int32_t forward_part(const ctr_step_t* d, int set, hipStream_t s, void* mark_beg
   return mark(mark_end, s);
 }
 
-// The rest of the step: interaction and its gradient (pooled step), then the backward with
-// the SGD update of the touched rows.
-int32_t backward_part(const ctr_step_t* d, int set, hipStream_t s, bool wait_unique,
-                      void* join_event) {
+// The interaction and its gradient (pooled step only).
+int32_t interaction_part(const ctr_step_t* d, hipStream_t s) {
+  if (d->kind != CTR_STEP_POOLED_INTERACTION) return CTR_OK;
   const int64_t F = (int64_t)d->num_tables + 1;
-  if (d->kind == CTR_STEP_POOLED_INTERACTION) {
-    CTR_TRY(ctr_dot_interaction_fwd(d->Z, d->batch, (int32_t)F, d->dim, d->compute, d->R,
-                                    d->dim + F * (F - 1) / 2, s));
-    CTR_TRY(ctr_dot_interaction_bwd(d->Z, d->dR, d->dim + F * (F - 1) / 2, d->batch, (int32_t)F,
-                                    d->dim, d->compute, d->dZ, s));
-  }
-  if (wait_unique) CTR_TRY(wait(s, join_event));
+  CTR_TRY(ctr_dot_interaction_fwd(d->Z, d->batch, (int32_t)F, d->dim, d->compute, d->R,
+                                  d->dim + F * (F - 1) / 2, s));
+  return ctr_dot_interaction_bwd(d->Z, d->dR, d->dim + F * (F - 1) / 2, d->batch, (int32_t)F,
+                                 d->dim, d->compute, d->dZ, s);
+}
+
+// The backward with the SGD update of the touched rows.
+int32_t sgd_part(const ctr_step_t* d, int set, hipStream_t s) {
+  const int64_t F = (int64_t)d->num_tables + 1;
   size_t wsb = d->ws_bwd_bytes;
   if (d->kind == CTR_STEP_POOLED_INTERACTION)
     return ctr_embbag_bwd_sgd(d->dZ + d->dim, F * d->dim, d->dim, d->offsets, d->batch,
@@ -133,8 +134,7 @@ int32_t ctr_step_run(const ctr_step_t* d, int64_t k, int32_t schedule, void* mai
   if (d->kind != CTR_STEP_POOLED_INTERACTION && d->kind != CTR_STEP_BATCH_MATRIX)
     return invalid("unknown step kind");
   if (k < 0) return invalid("step index k < 0");
-  if (schedule != CTR_SCHEDULE_SERIAL && schedule != CTR_SCHEDULE_PIPELINED &&
-      schedule != CTR_SCHEDULE_PIPELINED_EARLY)
+  if (schedule < CTR_SCHEDULE_SERIAL || schedule > CTR_SCHEDULE_PIPELINED_OVERLAP)
     return invalid("unknown schedule");
   if (side_stream && (!fork_event || !join_event))
     return invalid("a side stream needs fork and join events");
@@ -156,12 +156,29 @@ int32_t ctr_step_run(const ctr_step_t* d, int64_t k, int32_t schedule, void* mai
       CTR_TRY(unique_into(d, 0, s));
     }
     CTR_TRY(forward_part(d, 0, s, mark_begin, mark_end));
-    return backward_part(d, 0, s, fork, join_event);
+    CTR_TRY(interaction_part(d, s));
+    if (fork) CTR_TRY(wait(s, join_event));
+    return sgd_part(d, 0, s);
+  }
+  const int cur = (int)(k & 1), nxt = cur ^ 1;
+  if (schedule == CTR_SCHEDULE_PIPELINED_OVERLAP) {
+    // Only what the data needs: the backward of batch k waits for batch k's unique (recorded
+    // as join_event in step k-1), and batch k+1's unique waits for the backward of step k-1
+    // (fork_event), which released that set.  Host order matters: main's wait is enqueued
+    // before this step re-records join_event.
+    CTR_TRY(forward_part(d, cur, s, mark_begin, mark_end));
+    CTR_TRY(interaction_part(d, s));
+    if (k > 0) CTR_TRY(wait(s, join_event));
+    else CTR_TRY(record(fork_event, s));
+    CTR_TRY(wait(side, fork_event));
+    CTR_TRY(unique_into(d, nxt, side));
+    CTR_TRY(record(join_event, side));
+    CTR_TRY(sgd_part(d, cur, s));
+    return record(fork_event, s);
   }
   // pipelined: batch k uses set k % 2 (filled during step k-1, or by ctr_step_unique before
   // the first step); batch k+1's unique fills the other set on the side stream, forked after
   // the pooling kernel (or when the step starts) and joined before the step ends
-  const int cur = (int)(k & 1), nxt = cur ^ 1;
   const bool early = schedule == CTR_SCHEDULE_PIPELINED_EARLY;
   if (!early) CTR_TRY(forward_part(d, cur, s, mark_begin, mark_end));
   CTR_TRY(record(fork_event, s));
@@ -169,7 +186,8 @@ int32_t ctr_step_run(const ctr_step_t* d, int64_t k, int32_t schedule, void* mai
   CTR_TRY(unique_into(d, nxt, side));
   CTR_TRY(record(join_event, side));
   if (early) CTR_TRY(forward_part(d, cur, s, mark_begin, mark_end));
-  CTR_TRY(backward_part(d, cur, s, false, join_event));
+  CTR_TRY(interaction_part(d, s));
+  CTR_TRY(sgd_part(d, cur, s));
   return wait(s, join_event);
 }
 

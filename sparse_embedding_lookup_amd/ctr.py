@@ -29,6 +29,7 @@ EXPORTED = [
 
 CTR_STEP_POOLED_INTERACTION, CTR_STEP_BATCH_MATRIX = 0, 1
 CTR_SCHEDULE_SERIAL, CTR_SCHEDULE_PIPELINED, CTR_SCHEDULE_PIPELINED_EARLY = 0, 1, 2
+CTR_SCHEDULE_PIPELINED_OVERLAP = 3
 
 
 class CtrStep(ctypes.Structure):

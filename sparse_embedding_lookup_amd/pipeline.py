@@ -378,37 +378,40 @@ class FrontEnd:
         ctr.ctr_step_unique(self.native(), 0)
         self._k = 0
 
-    @staticmethod
-    def schedule_code(pipelined: bool, early: bool = True) -> int:
-        """ctr_step_run's schedule: serial, or pipelined with the next batch's unique forked
-        when the step starts (early) or right after the pooling kernel."""
-        if not pipelined:
-            return ctr.CTR_SCHEDULE_SERIAL
-        return ctr.CTR_SCHEDULE_PIPELINED_EARLY if early else ctr.CTR_SCHEDULE_PIPELINED
+    SCHEDULES = {"serial": ctr.CTR_SCHEDULE_SERIAL,
+                 "after-pooling": ctr.CTR_SCHEDULE_PIPELINED,
+                 "early": ctr.CTR_SCHEDULE_PIPELINED_EARLY,
+                 "overlap": ctr.CTR_SCHEDULE_PIPELINED_OVERLAP}
 
-    def step_native(self, pipelined: bool = False, mark_begin=None, mark_end=None,
-                    early: bool = True):
-        """One whole step in one native call (ctr_step_run); mark_begin/mark_end (optional
-        torch.cuda.Event) bracket the pooling kernel.  After it, the unique outputs of the
-        step's batch are the attributes (set k % 2 when pipelined)."""
-        assert self.pipelined or not pipelined, "the pipelined schedule needs two buffer sets"
+    def step_native(self, schedule: str = "serial", mark_begin=None, mark_end=None):
+        """One whole step in one native call (ctr_step_run) under `schedule` (a key of
+        SCHEDULES; the pipelined ones need FrontEnd(pipelined=True) and native_start() before
+        the first step); mark_begin/mark_end (optional torch.cuda.Event) bracket the pooling
+        kernel.  After it, the unique outputs of the step's batch are the attributes (set
+        k % 2 when pipelined).  With "overlap" the next batch's unique may still be running
+        on the side stream: native_join() (or a device synchronize) before reading it."""
+        code = self.SCHEDULES[schedule]
+        pipelined = code != ctr.CTR_SCHEDULE_SERIAL
+        assert self.pipelined or not pipelined, "the pipelined schedules need two buffer sets"
         d = self.native()
         k = self._k
-        ctr.ctr_step_run(d, k, self.schedule_code(pipelined, early),
-                         torch.cuda.current_stream(self.device), self.side, self._ev_fork,
-                         self._ev_join, mark_begin, mark_end)
+        ctr.ctr_step_run(d, k, code, torch.cuda.current_stream(self.device), self.side,
+                         self._ev_fork, self._ev_join, mark_begin, mark_end)
         self._use_set((k & 1) if pipelined else 0)
         self._k = k + 1
 
-    def capture_native(self, steps: int, pipelined: bool, marks=None, early: bool = True,
-                       side=None):
-        """Record `steps` consecutive native steps (k = 0 .. steps-1; even for the pipelined
-        schedule, whose set 0 must be primed before each replay sequence) into one HIP graph.
-        marks: optional list of 2*steps timing events around each step's pooling kernel, left
-        timed by every replay."""
-        assert not pipelined or (self.pipelined and steps % 2 == 0)
+    def native_join(self):
+        """Make the current stream wait for the side stream (the overlapped unique)."""
+        torch.cuda.current_stream(self.device).wait_stream(self.side)
+
+    def capture_native(self, steps: int, schedule: str = "serial", marks=None, side=None):
+        """Record `steps` consecutive native steps (k = 0 .. steps-1; an even count for the
+        pipelined schedules, whose set 0 must be primed before each replay) into one HIP
+        graph, ending with a join of the side stream.  marks: optional list of 2*steps timing
+        events around each step's pooling kernel, left timed by every replay."""
+        code = self.SCHEDULES[schedule]
+        assert code == ctr.CTR_SCHEDULE_SERIAL or (self.pipelined and steps % 2 == 0)
         d = self.native()
-        sched = self.schedule_code(pipelined, early)
         side = side if side is not None else self.side
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
@@ -416,7 +419,8 @@ class FrontEnd:
             for i in range(steps):
                 m0 = marks[2 * i] if marks else None
                 m1 = marks[2 * i + 1] if marks else None
-                ctr.ctr_step_run(d, i, sched, cap, side, self._ev_fork, self._ev_join, m0, m1)
+                ctr.ctr_step_run(d, i, code, cap, side, self._ev_fork, self._ev_join, m0, m1)
+            cap.wait_stream(side)
         self._use_set(0)
         return g
 

@@ -561,16 +561,17 @@ def test_pipelined_schedule_matches_serial(name, graphs):
         assert torch.equal(fa.table, fb.table)
 
 
-@pytest.mark.parametrize("pipelined", [False, True])
+@pytest.mark.parametrize("schedule", ["serial", "after-pooling", "early", "overlap"])
 @pytest.mark.parametrize("name", ["small_b256", "criteo_b128", "tensornet_b512"])
-def test_native_step_matches_python_steps(name, pipelined):
+def test_native_step_matches_python_steps(name, schedule):
     """ctr_step_run (the whole step in one native call) leaves the table, the forward outputs
     and the row gradients bit-identical to the same schedule driven call by call."""
     w = {"small_b256": lambda: workloads.small(batch=256),
          "criteo_b128": lambda: workloads.criteo(batch=128),
          "tensornet_b512": lambda: workloads.tensornet(batch=512, slots=100,
                                                        table_rows=500_000)}[name]()
-    say("native step", name, "pipelined" if pipelined else "serial")
+    say("native step", name, schedule)
+    pipelined = schedule != "serial"
     fa = FrontEnd(w, DEV, keep_grads=True, pipelined=pipelined)
     fb = FrontEnd(w, DEV, keep_grads=True, pipelined=pipelined)
     if pipelined:
@@ -581,7 +582,7 @@ def test_native_step_matches_python_steps(name, pipelined):
             fa.step_pipelined(fork_after="embbag_fwd")
         else:
             fa.step()
-        fb.step_native(pipelined=pipelined)
+        fb.step_native(schedule)
         torch.cuda.synchronize()
         U = int(host(fa.num_unique)[0])
         assert U == int(host(fb.num_unique)[0])
@@ -596,16 +597,17 @@ def test_native_step_matches_python_steps(name, pipelined):
         assert torch.equal(fa.table, fb.table)
 
 
-@pytest.mark.parametrize("pipelined", [False, True])
+@pytest.mark.parametrize("schedule", ["serial", "early", "overlap"])
 @pytest.mark.parametrize("name", ["small_b256", "tensornet_b512"])
-def test_native_step_graph_matches_eager(name, pipelined):
+def test_native_step_graph_matches_eager(name, schedule):
     """Native steps captured as one HIP graph (the timing marks as event-record nodes) and
     replayed twice, with unrelated eager work and synchronizations in between, leave the same
     table, outputs and row gradients as the same steps run eagerly; every mark pair comes
     back timed."""
     w = (workloads.small(batch=256) if name == "small_b256"
          else workloads.tensornet(batch=512, slots=100, table_rows=500_000))
-    say("native graph", name, "pipelined" if pipelined else "serial")
+    say("native graph", name, schedule)
+    pipelined = schedule != "serial"
     K = 4
     fa = FrontEnd(w, DEV, keep_grads=True, pipelined=True)
     fb = FrontEnd(w, DEV, keep_grads=True, pipelined=True)
@@ -613,7 +615,7 @@ def test_native_step_graph_matches_eager(name, pipelined):
     for m in marks:
         m.record()
     torch.cuda.synchronize()
-    g = fb.capture_native(K, pipelined, marks)
+    g = fb.capture_native(K, schedule, marks)
     if pipelined:
         fa.native_start()
     junk = torch.randn(1 << 20, device=DEV)
@@ -621,7 +623,7 @@ def test_native_step_graph_matches_eager(name, pipelined):
         if pipelined:
             fb.native_start()
         for _ in range(K):
-            fa.step_native(pipelined)
+            fa.step_native(schedule)
         g.replay()
         junk.mul_(1.0001).add_(1.0)
         torch.cuda.synchronize()
