@@ -56,6 +56,17 @@ WORKLOAD_NAMES = {
 }
 
 
+def compulsory_bytes(w, U, stage):
+    """The pooled gather's bytes with each distinct row read once (U rows instead of nnz)."""
+    assert stage == "embbag_fwd"
+    n, d = w.nnz, w.dim
+    if w.interaction:
+        rb = d * (2 if w.dtype == "bf16" else 4)
+        nb = w.num_tables * w.batch
+        return U * rb + 8 * n + 8 * (nb + 1) + 4 * nb * d
+    return U * 4 * d + 4 * n + 8 * (n + 1) + 4 * n * d
+
+
 def stage_bytes(w, U):
     """Algorithmic bytes moved by each stage (what the method must read and write)."""
     n = w.nnz
@@ -180,6 +191,9 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="small", choices=sorted(WORKLOAD_NAMES))
+    ap.add_argument("--ids", default="zipf", choices=["zipf", "uniform"],
+                    help="zipf: the workload's power-law IDs; uniform: the same shapes with "
+                         "uniform IDs (the control where caches cannot help)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--detail", default="", help="write per-stage detail JSON here")
@@ -213,7 +227,8 @@ def main():
 
     ctr.load()
     print("[bench] generating workload %s" % args.config, file=sys.stderr, flush=True)
-    w = workloads.make(args.config)
+    w = workloads.make(args.config) if args.ids == "zipf" else workloads.make(args.config,
+                                                                              ids=args.ids)
     print("[bench] nnz=%d, building device state" % w.nnz, file=sys.stderr, flush=True)
     graph = args.launch == "graph"
     native = args.launch in ("native", "graph")
@@ -388,7 +403,9 @@ def main():
                      if pipelined else "serial: each step dedups its own batch"),
         "ms_per_step_serial": ms_serial if pipelined else ms_step,   # null unless compared
         "data": "synthetic (seeded; tables from the counter-based fill)",
-        "config": {"workload": WORKLOAD_NAMES[args.config], "name": args.config,
+        "config": {"workload": WORKLOAD_NAMES[args.config] + (
+                       "" if args.ids == "zipf" else "; control: uniform IDs, same shapes"),
+                   "name": args.config, "ids": args.ids,
                    "batch": w.batch, "tables": w.num_tables, "dim": w.dim, "nnz": w.nnz,
                    "unique_rows": U},
         "hbm_gbps_algorithmic": step_bytes / (ms_step * 1e-3) / 1e9,
@@ -398,10 +415,15 @@ def main():
         "stage_ms": {k: round(v, 5) for k, v in stage_ms.items()},
         "roofline": {"kernel": dominant, "bound": "hbm", "achieved": achieved,
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
-                     "traffic": measured_traffic(args.config, dominant),
+                     "traffic": measured_traffic(
+                         args.config if args.ids == "zipf" else args.config + "_" + args.ids,
+                         dominant),
                      "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE+WRITE_SIZE)",
                      "bytes_per_launch": byts[dominant],
-                     "avg_launch_ms": dom_ms},
+                     "avg_launch_ms": dom_ms,
+                     "compulsory_bytes": compulsory_bytes(w, U, dominant),
+                     "compulsory_frac": compulsory_bytes(w, U, dominant) / (dom_ms * 1e-3) / 1e9
+                     / HBM_PEAK_GBPS},
     }
     if not args.no_cpu:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)

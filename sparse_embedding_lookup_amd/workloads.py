@@ -133,14 +133,23 @@ def tiny(seed: int = 0) -> Workload:
                     0.01, "f32")
 
 
-def small(seed: int = 0, batch: int = 2048, rows: int = 1_000_000) -> Workload:
-    """8 fp32 tables x 1M rows x d=64, B=2048, Poisson(20) bags in [1,100], Zipf(1.05) IDs."""
+def _row_ids(rng: np.random.Generator, ids: str, alpha: float, rows: int, size: int) -> np.ndarray:
+    """Row indices in [0, rows): bounded Zipf(alpha) ranks minus one, or uniform (the control
+    workload with the same shapes, where caches cannot help)."""
+    if ids == "uniform":
+        return rng.integers(0, rows, size=size, dtype=np.int64)
+    return bounded_zipf(rng, alpha, rows, size) - 1
+
+
+def small(seed: int = 0, batch: int = 2048, rows: int = 1_000_000, ids: str = "zipf") -> Workload:
+    """8 fp32 tables x 1M rows x d=64, B=2048, Poisson(20) bags in [1,100], Zipf(1.05) IDs
+    (ids="uniform": uniform IDs)."""
     T, d = 8, 64
     rng = np.random.default_rng(seed)
     lengths = np.clip(rng.poisson(20, size=(T, batch)), 1, 100)      # draw 1
     parts = []
     for t in range(T):                                                 # draw 2 (per table)
-        parts.append(bounded_zipf(rng, 1.05, rows, int(lengths[t].sum())) - 1)
+        parts.append(_row_ids(rng, ids, 1.05, rows, int(lengths[t].sum())))
     idx = np.concatenate(parts)
     dense = rng.standard_normal((batch, d)).astype(np.float32)        # draw 3
     F = T + 1
@@ -149,7 +158,7 @@ def small(seed: int = 0, batch: int = 2048, rows: int = 1_000_000) -> Workload:
                     _offsets_from_lengths(lengths), dense, grad, 0.01, "f32")
 
 
-def criteo(seed: int = 0, batch: int = 8192, row_scale: float = 1.0) -> Workload:
+def criteo(seed: int = 0, batch: int = 8192, row_scale: float = 1.0, ids: str = "zipf") -> Workload:
     """26 bf16 tables (rows log-uniform in [1e3,1e7]) x d=128, B=8192, 13 log-normal dense
     features projected to 128 by a fixed random matrix; tables 0-12 one-hot, 13-25 bags
     with lengths Zipf(1.1) on [1,64]; IDs Zipf(1.1)."""
@@ -161,7 +170,7 @@ def criteo(seed: int = 0, batch: int = 8192, row_scale: float = 1.0) -> Workload
     lengths[13:] = bounded_zipf(rng, 1.1, 64, (T - 13, batch))                 # draw 2
     parts = []
     for t in range(T):                                                          # draw 3
-        parts.append(bounded_zipf(rng, 1.1, int(rows[t]), int(lengths[t].sum())) - 1)
+        parts.append(_row_ids(rng, ids, 1.1, int(rows[t]), int(lengths[t].sum())))
     idx = np.concatenate(parts)
     raw = rng.lognormal(0.0, 1.0, size=(batch, 13))                             # draw 4
     proj = rng.normal(0.0, 1.0 / math.sqrt(13.0), size=(13, d))                 # draw 5
@@ -175,20 +184,25 @@ def criteo(seed: int = 0, batch: int = 8192, row_scale: float = 1.0) -> Workload
 
 
 def tensornet(seed: int = 0, batch: int = 65536, slots: int = 100,
-              table_rows: int = 20_000_000, key_space: int = 100_000_000_000) -> Workload:
+              table_rows: int = 20_000_000, key_space: int = 100_000_000_000,
+              ids: str = "zipf") -> Workload:
     """65,536 samples x 100 slots of 64-bit IDs, Zipf(1.2) over a 1e11 key space, rows =
     id mod 2e7 of one fp32 table of d=32; one ID per (sample, slot)."""
     d = 32
     rng = np.random.default_rng(seed)
-    ids = unbounded_zipf_capped(rng, 1.2, key_space, batch * slots)           # draw 1
+    if ids == "uniform":
+        raw = rng.integers(1, key_space + 1, size=batch * slots, dtype=np.int64)  # draw 1
+    else:
+        raw = unbounded_zipf_capped(rng, 1.2, key_space, batch * slots)       # draw 1
     grad = rng.standard_normal((batch, slots, d)).astype(np.float32)          # draw 2
     # Occurrence i = b*slots + s; every (sample, slot) bag holds exactly one ID.
     offsets = np.arange(batch * slots + 1, dtype=np.int64)
-    return Workload("tensornet", 1, [table_rows], d, "f32", batch, ids, offsets, None, grad,
+    return Workload("tensornet", 1, [table_rows], d, "f32", batch, raw, offsets, None, grad,
                     0.01, "f32", key_modulus=table_rows, slots=slots, interaction=False)
 
 
-def large(seed: int = 0, batch: int = 32768, tables: int = 64, rows: int = 4_000_000) -> Workload:
+def large(seed: int = 0, batch: int = 32768, tables: int = 64, rows: int = 4_000_000,
+          ids: str = "zipf") -> Workload:
     """64 bf16 tables x 4M rows x d=128, B=32768, Poisson(32) bags in [1,256], Zipf(1.1)
     IDs through a per-table random permutation of the hot ranks."""
     T, d = tables, 128
@@ -196,6 +210,9 @@ def large(seed: int = 0, batch: int = 32768, tables: int = 64, rows: int = 4_000
     lengths = np.clip(rng.poisson(32, size=(T, batch)), 1, 256)                # draw 1
     parts = []
     for t in range(T):                                                          # draw 2 (per table)
+        if ids == "uniform":
+            parts.append(rng.integers(0, rows, size=int(lengths[t].sum()), dtype=np.int64))
+            continue
         perm = rng.permutation(rows).astype(np.int64)
         k = bounded_zipf(rng, 1.1, rows, int(lengths[t].sum()))
         parts.append(perm[k - 1])
