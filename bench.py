@@ -97,7 +97,7 @@ def stage_bytes(w, U):
 # Stages that are one kernel launch each (a roofline needs one kernel's duration), with the
 # kernel's name prefix and source file.
 SINGLE_KERNEL = {
-    "embbag_fwd": ("embbag_fwd_kernel", "embbag.hip"),
+    "embbag_fwd": ("embbag_fwd_", "embbag.hip"),
     "interaction_fwd": ("interaction_fwd_", "interaction.hip"),
     "interaction_bwd": ("interaction_bwd_", "interaction.hip"),
     "sparse_sgd": ("sparse_sgd_kernel", "embbag.hip"),
@@ -127,13 +127,25 @@ def measured_traffic(config: str, stage: str):
     return None
 
 
-def cpu_baseline(w, seconds: float):
-    """The oracle, as it stands, on repeated full batches until `seconds` of CPU time."""
+def cpu_baseline(w, seconds: float, threads: int = 0):
+    """The oracle, as it stands, on repeated full batches until `seconds` of CPU time, on
+    `threads` OpenMP threads (0: the oracle's default, every host core)."""
     import numpy as np
     from oracle import oracle as orc
 
     from sparse_embedding_lookup_amd import workloads
 
+    default_threads = orc.get_threads()
+    if threads:
+        orc.set_threads(threads)
+    try:
+        return _cpu_baseline(w, seconds, orc, np, workloads)
+    finally:
+        if threads:
+            orc.set_threads(default_threads)
+
+
+def _cpu_baseline(w, seconds, orc, np, workloads):
     threads = orc.get_threads()
     tab = orc.Table(w.rows, w.dim, w.dtype, w.table_seed)
     if w.total_rows * w.dim * 4 <= (4 << 30):
@@ -195,6 +207,12 @@ def main():
                     help="zipf: the workload's power-law IDs; uniform: the same shapes with "
                          "uniform IDs (the control where caches cannot help)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--cpu-1thread-seconds", type=float, default=6.0,
+                    help="also time the oracle on one thread (Tiny, Small and Criteo only); "
+                         "0 skips it")
+    ap.add_argument("--cold-steps", type=int, default=5,
+                    help="per-stage timings with the caches flushed before every stage "
+                         "(1 GiB written and read); 0 skips them")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--detail", default="", help="write per-stage detail JSON here")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MB",
@@ -286,13 +304,33 @@ def main():
             e1.record()
     torch.cuda.synchronize()
     stage_ms = {n: sum(e0.elapsed_time(e1) for e0, e1 in evs[n]) / K for n in names}
+    # The same, cold: before every stage a 1 GiB buffer is written and then read, so that
+    # neither the L2s nor the 256 MB MALL hold any of the stage's inputs (or dirty lines).
+    stage_ms_cold = None
+    if args.cold_steps > 0:
+        flush = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+        cold = {n: [] for n in names}
+        for k in range(args.cold_steps):
+            for n in names:
+                flush.fill_(float(k))
+                flush.sum()
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                stage_runs[n]()
+                e1.record()
+                cold[n].append((e0, e1))
+        torch.cuda.synchronize()
+        stage_ms_cold = {n: sum(a.elapsed_time(b) for a, b in cold[n]) / len(cold[n])
+                         for n in names}
+        del flush, cold
     byts = stage_bytes(w, U)
     # the roofline's kernel: the single-kernel stage that moves the most algorithmic bytes
     # (the pooled gather on every workload); fixed by the workload, not by a timing
     dominant = max((s for s in stage_ms if s in SINGLE_KERNEL), key=lambda s: byts[s])
     if native:
-        # ctr_step_run brackets the pooling kernel with the timing events
-        assert dominant == "embbag_fwd", dominant
+        # ctr_step_run brackets the pooling kernel with the timing events; on the Tiny batch
+        # (launch-bound, every kernel a few microseconds) another stage may move more bytes
+        dominant = "embbag_fwd"
         warm()
     elif pipelined:
         # the next batch's unique and the stages after the dominant kernel replay from captured
@@ -413,6 +451,8 @@ def main():
                                                   stage_ms["interaction_bwd"]) * 1e-3)
                                       if w.interaction else None),
         "stage_ms": {k: round(v, 5) for k, v in stage_ms.items()},
+        "stage_ms_cold": ({k: round(v, 5) for k, v in stage_ms_cold.items()}
+                          if stage_ms_cold else None),
         "roofline": {"kernel": dominant, "bound": "hbm", "achieved": achieved,
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
                      "traffic": measured_traffic(
@@ -423,12 +463,19 @@ def main():
                      "avg_launch_ms": dom_ms,
                      "compulsory_bytes": compulsory_bytes(w, U, dominant),
                      "compulsory_frac": compulsory_bytes(w, U, dominant) / (dom_ms * 1e-3) / 1e9
-                     / HBM_PEAK_GBPS},
+                     / HBM_PEAK_GBPS,
+                     # the kernel alone with cold caches (per-stage timing after a flush)
+                     "cold_frac": (byts[dominant] / (stage_ms_cold[dominant] * 1e-3) / 1e9
+                                   / HBM_PEAK_GBPS if stage_ms_cold else None)},
     }
     if not args.no_cpu:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
         cb = cpu_baseline(w, args.cpu_seconds)
         out["cpu_baseline"] = {k: cb[k] for k in ("value", "unit", "cores", "kind", "sample")}
+        if args.cpu_1thread_seconds > 0 and args.config in ("tiny", "small", "criteo"):
+            cb1 = cpu_baseline(w, args.cpu_1thread_seconds, threads=1)
+            out["cpu_baseline_1thread"] = {k: cb1[k] for k in ("value", "unit", "cores", "kind",
+                                                               "sample")}
     if args.detail:
         det = dict(out)
         det["stage_bytes"] = byts

@@ -36,7 +36,8 @@
  *   - Device counts (num_unique) stay on the device; consumers read them there and launch
  *     for the capacity.
  *   - Calls that take `workspace` use a two-call query: with workspace == NULL the call only
- *     stores the required byte count in *workspace_bytes and returns CTR_OK.
+ *     stores the required byte count in *workspace_bytes and returns CTR_OK.  A workspace
+ *     must be 16-byte aligned (CTR_ERR_UNSUPPORTED otherwise).
  *   - Tables: all tables of a model live in ONE row-major allocation [total_rows, dim] of
  *     fp32 or bf16 (16-byte aligned); table t owns rows [row_base[t], row_base[t+1]).
  *     Bags are CSR, table-major: bag (t, b) spans indices[offsets[t*batch+b] ..

@@ -102,6 +102,7 @@ int32_t ctr_unique_ids(const void* ids, int32_t id_type, int64_t n, const int64_
   }
   if (*workspace_bytes < need)
     return fail(CTR_ERR_WORKSPACE_TOO_SMALL, "workspace %zu < %zu bytes", *workspace_bytes, need);
+  if (!aligned16(workspace)) return fail(CTR_ERR_UNSUPPORTED, "workspace is not 16-byte aligned");
   if (!num_unique) return fail(CTR_ERR_INVALID_ARGUMENT, "num_unique is NULL");
   if (n > 0 && (!ids || !uniq || !inverse))
     return fail(CTR_ERR_INVALID_ARGUMENT, "ids, uniq and inverse are required");

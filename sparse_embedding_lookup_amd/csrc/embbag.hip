@@ -2,10 +2,11 @@
 // fetch, the sparse SGD row update, the counter-based table fill and a CSR checker.
 //
 // Layout of the work: a row of the table is `vecs` 16-byte vectors (fp32: 4 values, bf16:
-// 8 values).  A group of G lanes (G a power of two, at most 64) owns one bag or one row; each
+// 8 values).  A group of G lanes (G a power of two, at most 64) reads one row at a time; each
 // lane loads VPL vectors per row with 128-bit loads, so a wavefront gathers 64/G rows per
-// load instruction.  Bags are handled by one group each with their row loads unrolled
-// kUnroll deep, which keeps enough bytes in flight per wave for random 128-512 B rows.
+// load instruction, and a group keeps kU row loads in flight.  Pooling splits a block's
+// bag-aligned occurrence range evenly over its groups (bags cut at group edges are joined in
+// LDS), so a long or heavy-tailed bag length does not set the kernel's tail.
 //
 // Pooling: "DHEN" notes, 2.1 "Feature Processing Layer" (one d-dim vector per sparse
 // feature; sum pooling is the reading taken).  Fetch into the batch-sized matrix and the
@@ -126,6 +127,184 @@ __global__ __launch_bounds__(kThreads) void embbag_fwd_kernel(
     }
   }
   while (cur < nb) flush(cur++);
+}
+
+// Balanced pooling: a block owns `nbb` consecutive bags (so its occurrence range starts and
+// ends on bag edges) and splits that range evenly over its kGroups lane groups; a group sums
+// the pieces of the bags in its share (rows in occurrence order, kU loads in flight), writes
+// the bags it holds whole straight out, and leaves the pieces of bags that cross a group
+// edge in LDS, where the group that holds a bag's first piece adds the following groups'
+// pieces in order.  A long bag thus costs what a short one does instead of setting the
+// kernel's tail.  Empty bags are written as zeros by one pass over the block's offsets.
+constexpr int kMaxBagsPerBlock = 1024;
+// Bags per block are picked so a lane group gets about kPoolRows occurrences, but the grid
+// keeps at least kPoolMinBlocks blocks (several per CU) unless a group would then get fewer
+// than kPoolMinRows occurrences (a short share leaves the kU-deep load window half empty).
+// Measured on the Small, Criteo-shaped, Large and TensorNet workloads.
+constexpr double kPoolRows = 128.0;
+constexpr int64_t kPoolMinBlocks = 2048;
+constexpr double kPoolMinRows = 20.0;
+
+template <typename TIdx, bool BF16, int G, int VPL>
+__global__ __launch_bounds__(kThreads) void embbag_fwd_balanced_kernel(
+    const char* __restrict__ table, int64_t total_rows, int64_t row_bytes, int vecs,
+    const int64_t* __restrict__ row_base, const TIdx* __restrict__ idx, int64_t nnz,
+    const int64_t* __restrict__ offsets, int64_t batch, int64_t num_bags, int nbb,
+    float* __restrict__ out, int64_t sb, int64_t st) {
+  constexpr int E = BF16 ? 8 : 4;
+  constexpr int kGroups = kThreads / G;
+  constexpr int kU = (VPL == 1 && G <= 8) ? 16 : 8;   // rows in flight per group
+  constexpr int kRegs = (kU + G - 1) / G;
+  constexpr int kW = G * VPL * E;                     // floats of one row piece
+  __shared__ int32_t s_off[kMaxBagsPerBlock + 1];     // nnz < 2^31
+  __shared__ int64_t s_base[kMaxBagsPerBlock];
+  __shared__ float s_first[kGroups][kW];              // piece that began before the share
+  __shared__ float s_last[kGroups][kW];               // piece that continues past the share
+  __shared__ int32_t s_fbag[kGroups], s_fcont[kGroups], s_lbag[kGroups];
+  const int lane = threadIdx.x & (G - 1);
+  const int grp = threadIdx.x / G;
+  const int lane0 = (threadIdx.x & 63) & ~(G - 1);
+  const int64_t s0 = (int64_t)blockIdx.x * nbb;
+  const int nb = (int)clamp64(num_bags - s0, 0, nbb);
+  for (int j = threadIdx.x; j <= nb; j += kThreads) s_off[j] = (int32_t)clamp64(offsets[s0 + j], 0, nnz);
+  for (int j = threadIdx.x; j < nb; j += kThreads) s_base[j] = row_base ? row_base[(s0 + j) / batch] : 0;
+  __syncthreads();
+  if (nb == 0) return;
+  auto base_of = [&](int c) -> int64_t { return s_base[c]; };
+  auto out_row = [&](int c) -> float* {
+    const int64_t sg = s0 + c;
+    const int64_t t = sg / batch, b = sg - t * batch;
+    return out + b * sb + t * st;
+  };
+  auto store = [&](float* o, const float (&acc)[VPL][E]) {
+#pragma unroll
+    for (int a = 0; a < VPL; ++a) {
+      const int vi = a * G + lane;
+      if (vi < vecs) {
+        float4* p = reinterpret_cast<float4*>(o + (int64_t)vi * E);
+        p[0] = make_float4(acc[a][0], acc[a][1], acc[a][2], acc[a][3]);
+        if (E == 8) p[1] = make_float4(acc[a][4 % E], acc[a][5 % E], acc[a][6 % E], acc[a][7 % E]);
+      }
+    }
+  };
+  auto to_lds = [&](float* dst, const float (&acc)[VPL][E]) {
+#pragma unroll
+    for (int a = 0; a < VPL; ++a)
+#pragma unroll
+      for (int e = 0; e < E; ++e) dst[(a * G + lane) * E + e] = acc[a][e];
+  };
+
+  const int64_t o_beg = s_off[0];
+  const int64_t range = (int64_t)s_off[nb] - o_beg;
+  const int64_t share = (range + kGroups - 1) / kGroups;
+  const int64_t q0 = o_beg + (int64_t)grp * share;
+  const int64_t q1 = q0 + share < o_beg + range ? q0 + share : o_beg + range;
+  int32_t fbag = -1, fcont = 0, lbag = -1;
+  if (q0 < q1) {
+    // bag of the share's first occurrence: last c with s_off[c] <= q0 (binary search)
+    int c = 0, hi = nb - 1;
+    while (c < hi) {
+      const int mid = (c + hi + 1) >> 1;
+      if ((int64_t)s_off[mid] <= q0) c = mid; else hi = mid - 1;
+    }
+    bool piece_at_start = q0 == s_off[c];
+    float acc[VPL][E];
+#pragma unroll
+    for (int a = 0; a < VPL; ++a)
+#pragma unroll
+      for (int e = 0; e < E; ++e) acc[a][e] = 0.f;
+    auto close_piece = [&](bool bag_ends_here) {
+      if (piece_at_start && bag_ends_here) {
+        store(out_row(c), acc);
+      } else if (!piece_at_start) {            // began before this share
+        fbag = c;
+        fcont = bag_ends_here ? 0 : 1;
+        to_lds(s_first[grp], acc);
+      } else {                                 // began here, continues past the share
+        lbag = c;
+        to_lds(s_last[grp], acc);
+      }
+#pragma unroll
+      for (int a = 0; a < VPL; ++a)
+#pragma unroll
+        for (int e = 0; e < E; ++e) acc[a][e] = 0.f;
+    };
+    for (int64_t k0 = q0; k0 < q1; k0 += kU) {
+      TIdx iv[kRegs];
+#pragma unroll
+      for (int r = 0; r < kRegs; ++r) {
+        const int e = r * G + lane;
+        const int64_t k = k0 + e;
+        iv[r] = (e < kU && k < q1) ? idx[k] : (TIdx)0;
+      }
+      uint4 rv[kU][VPL];
+      int bagu[kU];
+      int cc = c;
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        const int64_t k = k0 + u;
+        while (cc < nb - 1 && k >= s_off[cc + 1]) ++cc;
+        bagu[u] = cc;
+        const int64_t id = (int64_t)__shfl(iv[u / G], lane0 + (u % G), 64);
+        const int64_t key = base_of(cc) + id;
+        const bool live = k < q1;
+        const bool ok = key >= 0 && key < total_rows;
+#pragma unroll
+        for (int a = 0; a < VPL; ++a) {
+          const int vi = a * G + lane;
+          if (live && ok && vi < vecs)
+            rv[u][a] = *reinterpret_cast<const uint4*>(table + key * row_bytes + (int64_t)vi * 16);
+          else if (live && !ok)
+            rv[u][a] = make_uint4(0x7FC00000u, 0x7FC00000u, 0x7FC00000u, 0x7FC00000u);  // NaN
+          else
+            rv[u][a] = make_uint4(0u, 0u, 0u, 0u);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        if (k0 + u >= q1) break;
+        if (bagu[u] != c) {                    // the piece of bag c ended at this occurrence
+          close_piece(true);
+          c = bagu[u];
+          piece_at_start = true;               // a later bag begins inside the share
+        }
+#pragma unroll
+        for (int a = 0; a < VPL; ++a) accumulate<BF16>(acc[a], rv[u][a]);
+      }
+    }
+    close_piece(q1 == s_off[c + 1]);
+  }
+  if (lane == 0) {
+    s_fbag[grp] = fbag;
+    s_fcont[grp] = fcont;
+    s_lbag[grp] = lbag;
+  }
+  __syncthreads();
+  // a bag that crosses share edges: its first piece's group adds the next groups' pieces
+  if (s_lbag[grp] != -1) {
+    const int c = s_lbag[grp];
+    float acc[VPL][E];
+#pragma unroll
+    for (int a = 0; a < VPL; ++a)
+#pragma unroll
+      for (int e = 0; e < E; ++e) acc[a][e] = s_last[grp][(a * G + lane) * E + e];
+    for (int j = grp + 1; j < kGroups && s_fbag[j] == c; ++j) {
+#pragma unroll
+      for (int a = 0; a < VPL; ++a)
+#pragma unroll
+        for (int e = 0; e < E; ++e) acc[a][e] += s_first[j][(a * G + lane) * E + e];
+      if (!s_fcont[j]) break;
+    }
+    store(out_row(c), acc);
+  }
+  // empty bags
+  for (int j = threadIdx.x; j < nb; j += kThreads) {
+    if (s_off[j] == s_off[j + 1]) {
+      float* o = out_row(j);
+      for (int c2 = 0; c2 < vecs * E; c2 += 4)
+        *reinterpret_cast<float4*>(o + c2) = make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+  }
 }
 
 // E[u] = W[rows[u]] widened to fp32, u < min(num_rows, capacity).
@@ -300,37 +479,55 @@ hipError_t launch_embbag_fwd(const void* table, bool bf16, int64_t total_rows, i
   const int64_t num_bags = (int64_t)num_tables * batch;
   if (num_bags == 0) return hipSuccess;
   const char* tb = static_cast<const char*>(table);
-  // Bags per lane group: about 64 occurrences per group, but keep >= 1024 blocks in flight.
   const double avg = (double)nnz / (double)num_bags;
-  int nbg = (int)(64.0 / (avg > 1.0 ? avg : 1.0) + 0.5);
-  if (nbg > kMaxBagsPerGroup) nbg = kMaxBagsPerGroup;
+#define CTR_FWD_LAUNCH(KERNEL, BLOCKS, PER)                                                    \
+  do {                                                                                        \
+    if (bf16) {                                                                               \
+      if (idx64)                                                                              \
+        KERNEL<int64_t, true, G, VPL><<<(unsigned)(BLOCKS), kThreads, 0, s>>>(                \
+            tb, total_rows, row_bytes, vecs, row_base, (const int64_t*)idx, nnz, offsets,     \
+            batch, num_bags, PER, out, sb, st);                                               \
+      else                                                                                    \
+        KERNEL<int32_t, true, G, VPL><<<(unsigned)(BLOCKS), kThreads, 0, s>>>(                \
+            tb, total_rows, row_bytes, vecs, row_base, (const int32_t*)idx, nnz, offsets,     \
+            batch, num_bags, PER, out, sb, st);                                               \
+    } else {                                                                                  \
+      if (idx64)                                                                              \
+        KERNEL<int64_t, false, G, VPL><<<(unsigned)(BLOCKS), kThreads, 0, s>>>(               \
+            tb, total_rows, row_bytes, vecs, row_base, (const int64_t*)idx, nnz, offsets,     \
+            batch, num_bags, PER, out, sb, st);                                               \
+      else                                                                                    \
+        KERNEL<int32_t, false, G, VPL><<<(unsigned)(BLOCKS), kThreads, 0, s>>>(               \
+            tb, total_rows, row_bytes, vecs, row_base, (const int32_t*)idx, nnz, offsets,     \
+            batch, num_bags, PER, out, sb, st);                                               \
+    }                                                                                         \
+  } while (0)
   CTR_DISPATCH_G_VPL(rg.G, rg.VPL, {
-    const int64_t groups_for_fill = (int64_t)(kThreads / G) * 1024;
-    const int64_t cap = num_bags / groups_for_fill;
+    constexpr int kGroups = kThreads / G;
+    if (VPL == 1) {
+      const double per = avg > 1.0 ? avg : 1.0;
+      int64_t nbb = (int64_t)(kPoolRows * kGroups / per + 0.5);
+      if (nbb > num_bags / kPoolMinBlocks) nbb = num_bags / kPoolMinBlocks;
+      const int64_t floor_bags = (int64_t)ceil(kPoolMinRows * kGroups / per);
+      if (nbb < floor_bags) nbb = floor_bags;
+      if (nbb > kMaxBagsPerBlock) nbb = kMaxBagsPerBlock;
+      if (nbb < 1) nbb = 1;
+      const int64_t blocks = (num_bags + nbb - 1) / nbb;
+      CTR_FWD_LAUNCH(embbag_fwd_balanced_kernel, blocks, (int)nbb);
+      break;
+    }
+    // Rows of 1 KiB and more (64 lanes, several vectors each): one group per few bags.
+    // Bags per lane group: about 64 occurrences per group, but keep >= 1024 blocks in flight.
+    int nbg = (int)(64.0 / (avg > 1.0 ? avg : 1.0) + 0.5);
+    if (nbg > kMaxBagsPerGroup) nbg = kMaxBagsPerGroup;
+    const int64_t cap = num_bags / ((int64_t)kGroups * 1024);
     if (nbg > cap) nbg = (int)cap;
     if (nbg < 1) nbg = 1;
-    const int64_t per_block = (int64_t)(kThreads / G) * nbg;
+    const int64_t per_block = (int64_t)kGroups * nbg;
     const int64_t blocks = (num_bags + per_block - 1) / per_block;
-    if (bf16) {
-      if (idx64)
-        embbag_fwd_kernel<int64_t, true, G, VPL><<<(unsigned)blocks, kThreads, 0, s>>>(
-            tb, total_rows, row_bytes, vecs, row_base, (const int64_t*)idx, nnz, offsets,
-            batch, num_bags, nbg, out, sb, st);
-      else
-        embbag_fwd_kernel<int32_t, true, G, VPL><<<(unsigned)blocks, kThreads, 0, s>>>(
-            tb, total_rows, row_bytes, vecs, row_base, (const int32_t*)idx, nnz, offsets,
-            batch, num_bags, nbg, out, sb, st);
-    } else {
-      if (idx64)
-        embbag_fwd_kernel<int64_t, false, G, VPL><<<(unsigned)blocks, kThreads, 0, s>>>(
-            tb, total_rows, row_bytes, vecs, row_base, (const int64_t*)idx, nnz, offsets,
-            batch, num_bags, nbg, out, sb, st);
-      else
-        embbag_fwd_kernel<int32_t, false, G, VPL><<<(unsigned)blocks, kThreads, 0, s>>>(
-            tb, total_rows, row_bytes, vecs, row_base, (const int32_t*)idx, nnz, offsets,
-            batch, num_bags, nbg, out, sb, st);
-    }
+    CTR_FWD_LAUNCH(embbag_fwd_kernel, blocks, nbg);
   });
+#undef CTR_FWD_LAUNCH
   return hipGetLastError();
 }
 

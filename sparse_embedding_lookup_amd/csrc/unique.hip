@@ -137,6 +137,8 @@ __global__ __launch_bounds__(kThreads) void form_keys_flat_kernel(const void* __
 // --------------------------------------------------------------------------- upsweep
 // Digit counts of each block's contiguous range; hist is digit-major: hist[digit * ld + block]
 // (ld = block count rounded up to 4), so one digit's counts over the blocks are contiguous.
+constexpr int kUpU = 4;   // keys in flight per thread in the upsweep
+
 template <typename K>
 __global__ __launch_bounds__(kThreads) void radix_upsweep_kernel(
     const K* __restrict__ keys, int64_t n, int shift, int nbits, int64_t per_block,
@@ -148,15 +150,31 @@ __global__ __launch_bounds__(kThreads) void radix_upsweep_kernel(
   const uint32_t mask = (1u << nbits) - 1u;
   const int64_t beg = (int64_t)blockIdx.x * per_block;
   const int64_t end = beg + per_block < n ? beg + per_block : n;
-  const uint64_t lt = lanemask_lt();
-  for (int64_t base = beg; base < end; base += kThreads) {
-    const int64_t e = base + threadIdx.x;
-    const bool valid = e < end;
-    const uint32_t d = valid ? (uint32_t)(keys[e] >> shift) & mask : 0u;
-    const uint64_t active = __ballot(valid);
-    const uint64_t m = match_digit(d, nbits, active);
-    if (valid && (m & lt) == 0) cnt[wave][d] += (uint32_t)__popcll(m);
+  // Counting needs no order: LDS atomic adds into the wave's own bins (lanes of one wave
+  // that share a digit are serialised by the LDS; waves never contend).  Keys are read as
+  // 16-byte vectors, kUpU per thread issued before any is counted; a range's last partial
+  // vector is read one key at a time.  (Block ranges start on multiples of 1024 keys.)
+  constexpr int V = 16 / (int)sizeof(K);
+  const int64_t vend = beg + ((end - beg) / V) * V;
+  for (int64_t base = beg; base < vend; base += (int64_t)kThreads * kUpU * V) {
+    uint4 raw[kUpU];
+#pragma unroll
+    for (int j = 0; j < kUpU; ++j) {
+      const int64_t e = base + ((int64_t)j * kThreads + threadIdx.x) * V;
+      raw[j] = *reinterpret_cast<const uint4*>(keys + (e < vend ? e : vend - V));
+    }
+#pragma unroll
+    for (int j = 0; j < kUpU; ++j) {
+      const int64_t e = base + ((int64_t)j * kThreads + threadIdx.x) * V;
+      if (e < vend) {
+        const K* kv = reinterpret_cast<const K*>(&raw[j]);
+#pragma unroll
+        for (int v = 0; v < V; ++v) atomicAdd(&cnt[wave][(uint32_t)(kv[v] >> shift) & mask], 1u);
+      }
+    }
   }
+  for (int64_t e = vend + threadIdx.x; e < end; e += kThreads)
+    atomicAdd(&cnt[wave][(uint32_t)(keys[e] >> shift) & mask], 1u);
   __syncthreads();
   const int d = threadIdx.x;
   hist[(int64_t)d * ld + blockIdx.x] = cnt[0][d] + cnt[1][d] + cnt[2][d] + cnt[3][d];

@@ -65,6 +65,10 @@ def test_unique_workspace_query_and_bad_args():
     st = lib.ctr_unique_ids(FAKE, 1, 1000, None, 0, 0, None, 0, 0, FAKE, FAKE, FAKE, None, None,
                             None, FAKE, ctypes.byref(bad), None)
     assert st == ctr.CTR_ERR_WORKSPACE_TOO_SMALL
+    big = ctypes.c_size_t(wsb.value)
+    st = lib.ctr_unique_ids(FAKE, 1, 1000, None, 0, 0, None, 0, 0, FAKE, FAKE, FAKE, None, None,
+                            None, MISALIGNED, ctypes.byref(big), None)
+    assert st == ctr.CTR_ERR_UNSUPPORTED and b"aligned" in lib.ctr_last_error()
     assert lib.ctr_unique_ids(FAKE, 1, -1, None, 0, 0, None, 0, 0, None, None, None, None, None,
                               None, None, ctypes.byref(wsb), None) == ctr.CTR_ERR_INVALID_ARGUMENT
     assert lib.ctr_unique_ids(FAKE, 1, 2 ** 31, None, 0, 0, None, 0, 0, None, None, None, None,

@@ -194,6 +194,12 @@ def _fwd_case(name):
         rows = [2000, 2000]
         ids, off = rand_csr(rng, 2, 100, rows, 20)
         return rows, 512, "f32", ids, off, 100, 2
+    if name == "mixed_tables_d64":
+        # tables of very different sizes; blocks of bags cross table edges and long bags
+        # cross the lane groups' shares of a block
+        rows = [7, 50_000, 300]
+        ids, off = rand_csr(rng, 3, 1001, rows, 64, empty_frac=0.1)
+        return rows, 64, "f32", ids, off, 1001, 3
     if name == "one_bag_200k":
         rows = [100_000]
         off = np.array([0, 200_000], dtype=np.int64)
@@ -203,7 +209,7 @@ def _fwd_case(name):
 
 
 FWD_CASES = ["tiny", "small_b512", "criteo_b512", "empty_bags_d4", "bf16_d8_long", "f32_d512",
-             "one_bag_200k"]
+             "mixed_tables_d64", "one_bag_200k"]
 
 
 @pytest.mark.parametrize("name", FWD_CASES)
