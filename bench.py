@@ -231,6 +231,9 @@ def main():
                          "its batch's unique only before its backward; steps overlap), early "
                          "(the next batch's unique forked at the step start, joined at its "
                          "end) or after-pooling (forked after the pooling kernel)")
+    ap.add_argument("--rounding", default="nearest", choices=["nearest", "stochastic"],
+                    help="bf16 tables: round the sparse update to nearest-even, or "
+                         "stochastically (a fresh counter-based seed per step)")
     ap.add_argument("--compare-serial", action="store_true",
                     help="after a pipelined run, also time K serial steps (ms_per_step_serial)")
     args = ap.parse_args()
@@ -254,7 +257,10 @@ def main():
     sched = args.pipeline if pipelined else "serial"
     if graph and pipelined and args.steps % 2:
         args.steps += 1                  # a pipelined graph holds whole pairs of steps
-    fe = FrontEnd(w, "cuda", pipelined=pipelined)
+    if args.rounding == "stochastic" and w.dtype != "bf16":
+        print("--rounding stochastic needs a bf16-table workload (criteo, large)", file=sys.stderr)
+        sys.exit(2)
+    fe = FrontEnd(w, "cuda", pipelined=pipelined, rounding=args.rounding)
     st = fe.stages()
     torch.cuda.synchronize()
     if args.copy_calibration:
@@ -443,7 +449,7 @@ def main():
         "data": "synthetic (seeded; tables from the counter-based fill)",
         "config": {"workload": WORKLOAD_NAMES[args.config] + (
                        "" if args.ids == "zipf" else "; control: uniform IDs, same shapes"),
-                   "name": args.config, "ids": args.ids,
+                   "name": args.config, "ids": args.ids, "rounding": args.rounding,
                    "batch": w.batch, "tables": w.num_tables, "dim": w.dim, "nnz": w.nnz,
                    "unique_rows": U},
         "hbm_gbps_algorithmic": step_bytes / (ms_step * 1e-3) / 1e9,

@@ -169,6 +169,19 @@ int32_t ctr_embbag_bwd_sgd(const float* grad, int64_t grad_stride_b, int64_t gra
                            size_t* workspace_bytes, void* stream);
 
 /*
+ * ctr_embbag_bwd_sgd_sr -- ctr_embbag_bwd_sgd for a CTR_BF16 table with stochastic rounding
+ * of the updated values (see ctr_sparse_sgd_sr for the rounding and its random bits);
+ * `seed` selects the random bits of this update.  Bit-identical to ctr_embbag_bwd followed
+ * by ctr_sparse_sgd_sr with the same seed.  A CTR_F32 table gives CTR_ERR_UNSUPPORTED.
+ */
+int32_t ctr_embbag_bwd_sgd_sr(const float* grad, int64_t grad_stride_b, int64_t grad_stride_t,
+                              const int64_t* offsets, int64_t batch, int32_t num_tables,
+                              int64_t nnz, const int32_t* sorted_src, const int32_t* num_unique,
+                              void* table, int32_t dtype, int64_t total_rows, int32_t dim,
+                              const int64_t* uniq, float lr, uint64_t seed, float* row_grads,
+                              void* workspace, size_t* workspace_bytes, void* stream);
+
+/*
  * ctr_sparse_sgd -- update of the touched rows only ([TN] "Synchronous Architecture"):
  *   table[uniq[u], :] = round(table[uniq[u], :] - lr * row_grads[u, :])
  * for u < min(num_unique[0], capacity), computed in fp32 (one fused multiply-add) and
@@ -178,6 +191,29 @@ int32_t ctr_embbag_bwd_sgd(const float* grad, int64_t grad_stride_b, int64_t gra
 int32_t ctr_sparse_sgd(void* table, int32_t dtype, int64_t total_rows, int32_t dim,
                        const int64_t* uniq, const int32_t* num_unique, int64_t capacity,
                        const float* row_grads, float lr, void* stream);
+
+/*
+ * ctr_sparse_sgd_sr -- ctr_sparse_sgd for a CTR_BF16 table, with stochastic rounding
+ * ("DHEN" notes, 6.4 "Common Optimizations": low-precision embeddings updated with
+ * stochastic rounding).  Element (key, c), key = uniq[u]:
+ *   x = fmaf(-lr, row_grads[u, c], table[key, c])            (binary32, rounded once)
+ *   r = bits 16e .. 16e+15 (e = c mod 4) of splitmix64 from state
+ *       seed ^ (key * dim + c - e)          (one generator output per 4 columns)
+ *   stored = lo + sign(x) * ulp   if r < the low 16 bits of x's binary32 pattern
+ *            lo                   otherwise
+ * where lo is x truncated toward zero to bf16: round away from zero with probability
+ * (|x| - |lo|) / ulp, so the stored value is x in expectation over r.  Exact values and
+ * infinities are kept, NaN stays NaN.  Use a fresh seed per update (ctr_sr_step_seed).
+ * A CTR_F32 table gives CTR_ERR_UNSUPPORTED.
+ */
+int32_t ctr_sparse_sgd_sr(void* table, int32_t dtype, int64_t total_rows, int32_t dim,
+                          const int64_t* uniq, const int32_t* num_unique, int64_t capacity,
+                          const float* row_grads, float lr, uint64_t seed, void* stream);
+
+/* ctr_sr_step_seed -- the seed of the k-th stochastically rounded update (k >= 0) of a run
+ * seeded with `base`: output k of the splitmix64 stream whose state starts at base, i.e. the
+ * state after k + 1 golden-ratio increments, mixed.  ctr_step_run uses it for step k. */
+uint64_t ctr_sr_step_seed(uint64_t base, int64_t k);
 
 /*
  * ctr_dot_interaction_fwd -- [DLRM] 02, [DHEN] 3.1 and Solution 2.  Z: fp32 [batch, F, dim]
@@ -231,7 +267,8 @@ int32_t ctr_validate_csr(const void* indices, int32_t index_type, int64_t nnz,
  *   CTR_STEP_POOLED_INTERACTION  tables + dense vector ("Meta DLRM" 02, "DHEN" notes 2.1):
  *     ctr_unique_ids over (indices, offsets, row_base) -> ctr_embbag_fwd into Z[:, 1:, :]
  *     -> ctr_dot_interaction_fwd (Z -> R) -> ctr_dot_interaction_bwd (dR -> dZ)
- *     -> ctr_embbag_bwd_sgd over dZ[:, 1:, :] (SGD on the touched rows).
+ *     -> ctr_embbag_bwd_sgd over dZ[:, 1:, :] (SGD on the touched rows; with
+ *     rounding == CTR_ROUND_STOCHASTIC, ctr_embbag_bwd_sgd_sr, in both kinds).
  *     Z, dZ: fp32 [batch, num_tables + 1, dim], Z[:, 0, :] = the dense vector (input);
  *     R, dR: fp32 [batch, dim + P], P = (num_tables + 1) * num_tables / 2.
  *   CTR_STEP_BATCH_MATRIX  one table, IDs mapped by key_modulus ([TN] "Core Optimizations"):
@@ -247,6 +284,7 @@ int32_t ctr_validate_csr(const void* indices, int32_t index_type, int64_t nnz,
  * (fp32 [nnz, dim]) is optional.
  */
 enum { CTR_STEP_POOLED_INTERACTION = 0, CTR_STEP_BATCH_MATRIX = 1 };
+enum { CTR_ROUND_NEAREST = 0, CTR_ROUND_STOCHASTIC = 1 };
 enum {
   CTR_SCHEDULE_SERIAL = 0,
   CTR_SCHEDULE_PIPELINED = 1,
@@ -288,6 +326,9 @@ typedef struct {
   int32_t* perm[2];               /* nullable */
   int32_t* seg_offsets[2];        /* nullable */
   int32_t* sorted_src[2];
+  int32_t rounding;               /* CTR_ROUND_NEAREST, or CTR_ROUND_STOCHASTIC (bf16 table):
+                                     step k updates with seed ctr_sr_step_seed(sr_seed, k) */
+  uint64_t sr_seed;
 } ctr_step_t;
 
 /*

@@ -24,8 +24,11 @@
  *           section "Synchronous Architecture": only features present in the batch move.
  *   [DLRM]  "Meta DLRM" (upskillscore.com), section 02: the interaction is the dot product
  *           between all pairs of embedding vectors and the processed dense features.
+ *           Section 6.4 "Common Optimizations": low-precision (FP16) embedding storage
+ *           whose updates use stochastic rounding.
  * Readings where the pages are silent (sum pooling, strict i > j pair order, sum of
- * gradients over the batch, RNE storage rounding) follow the plain definitions below.
+ * gradients over the batch, RNE storage rounding, the stochastic-rounding rule and its
+ * random bits) follow the plain definitions below.
  */
 #include <math.h>
 #include <stdint.h>
@@ -337,5 +340,55 @@ void orc_sparse_sgd(const float* data, uint64_t seed, const int64_t* row_base,
       double x = w - l * g[u * dim + c];
       new_rows[u * dim + c] = bf16 ? orc_round_bf16(x) : orc_round_f32(x);
       nmag[u * dim + c] = fabs(w) + l * gmag[u * dim + c];
+    }
+}
+
+/* ------------------------------------------------------------------ stochastic rounding */
+/* [DHEN] 6.4 names stochastic rounding for low-precision embedding updates and gives no
+ * formula; the textbook definition is taken, for bfloat16 storage.  x lies between the
+ * adjacent bfloat16 values lo (toward zero) and hi = lo + sign(x) * quantum (away from
+ * zero); SR(x) = hi with probability p = (|x| - |lo|) / quantum, else lo.  The probability
+ * is realised by a uniform 16-bit integer r: hi iff r < p * 2^16.  For a binary32 x, p is
+ * a multiple of 2^-16, so over all 2^16 values of r the mean of SR(x) is exactly x.
+ * Exact values (p = 0), zeros, infinities and NaN come back unchanged; a value above the
+ * largest finite bfloat16 that rounds up becomes infinity. */
+double orc_sr_bf16(double x, uint32_t r) {
+  if (x == 0.0 || isnan(x) || isinf(x)) return x;
+  int e;
+  frexp(x, &e);
+  int q = e - 8;                 /* exponent of the last kept bit, as in orc_round_bf16 */
+  if (q < -133) q = -133;
+  double quantum = ldexp(1.0, q);
+  double lo = ldexp(trunc(ldexp(x, -q)), q);
+  double p = (fabs(x) - fabs(lo)) / quantum;       /* exact, in [0, 1) */
+  double out = ((double)r < p * 65536.0) ? lo + copysign(quantum, x) : lo;
+  if (fabs(out) > 3.3895313892515355e38) out = copysign(INFINITY, x);
+  return out;
+}
+
+/* Random bits of element (key, col) of an update drawn with seed s: columns are taken in
+ * groups of four, c4 = col - col mod 4; one splitmix64 output from state s ^ (key*dim + c4)
+ * (the same generator as the table fill, a fresh seed per update) gives 64 bits, and
+ * column c4 + e takes bits 16e .. 16e+15 of it. */
+uint32_t orc_sr_bits(uint64_t seed, int64_t key, int64_t col, int32_t dim) {
+  int64_t e = col % 4;
+  uint64_t st = seed ^ (uint64_t)(key * (int64_t)dim + (col - e));
+  return (uint32_t)((orc_splitmix64_next(&st) >> (16 * e)) & 0xFFFFu);
+}
+
+/* a9 with stochastic rounding, bfloat16 storage: W[uniq[u]] <- SR(x) with
+ * x = fmaf(-lr, g[u], W[uniq[u]]), the binary32 fused multiply-add rounded once.  The value
+ * that decides the rounding is taken in binary32, the precision the update kernel computes
+ * in (g is binary32 here).  new_rows: [U][dim]. */
+void orc_sparse_sgd_sr(const float* data, uint64_t seed, const int64_t* row_base,
+                       int32_t num_tables, int32_t dim, const int64_t* uniq, int64_t U,
+                       const float* g, float lr, uint64_t sr_seed, double* new_rows) {
+  orc_table tb = {data, seed, row_base, num_tables, dim, 1};
+#pragma omp parallel for schedule(static)
+  for (int64_t u = 0; u < U; ++u)
+    for (int64_t c = 0; c < dim; ++c) {
+      float w = (float)tval(&tb, uniq[u], c);
+      float x = fmaf(-lr, g[u * dim + c], w);
+      new_rows[u * dim + c] = orc_sr_bf16((double)x, orc_sr_bits(sr_seed, uniq[u], c, dim));
     }
 }

@@ -57,6 +57,9 @@ def _load():
         "orc_interaction_bwd": (None, [P, P, P, i64, i32, i32, P, P]),
         "orc_embbag_bwd": (None, [P, P, P, i64, i32, i32, P, i64, P, P]),
         "orc_sparse_sgd": (None, [P, u64, P, i32, i32, i32, P, i64, P, P, f32, P, P]),
+        "orc_sr_bf16": (f64, [f64, ctypes.c_uint32]),
+        "orc_sr_bits": (ctypes.c_uint32, [u64, i64, i64, i32]),
+        "orc_sparse_sgd_sr": (None, [P, u64, P, i32, i32, P, i64, P, f32, u64, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -229,3 +232,26 @@ def sparse_sgd(tab: Table, uniq, g, gmag, lr: float):
     _load().orc_sparse_sgd(*tab.args(), _p(uniq), U, _p(g), _p(gm), ctypes.c_float(lr),
                            _p(out), _p(nm))
     return out, nm
+
+
+def sr_bf16(x: float, r: int) -> float:
+    """Stochastic rounding of x to bfloat16 with the 16-bit random integer r."""
+    return float(_load().orc_sr_bf16(float(x), int(r) & 0xFFFF))
+
+
+def sr_bits(seed: int, key: int, col: int, dim: int) -> int:
+    """The 16 random bits of element (key, col) of an update drawn with `seed`."""
+    return int(_load().orc_sr_bits(seed & 0xFFFFFFFFFFFFFFFF, int(key), int(col), int(dim)))
+
+
+def sparse_sgd_sr(tab: Table, uniq, g, lr: float, sr_seed: int):
+    """Updated stored values (bf16 table) of rows ``uniq`` with stochastic rounding:
+    SR(fmaf(-lr, g, w)) per element, g binary32 [U, dim].  Returns float64 [U, dim]."""
+    assert tab.bf16, "stochastic rounding is defined for bf16 storage"
+    uniq = _c(uniq, np.int64)
+    g = _c(g, np.float32)
+    U = uniq.size
+    out = np.empty((U, tab.dim), dtype=np.float64)
+    _load().orc_sparse_sgd_sr(*tab.args()[:5], _p(uniq), U, _p(g), ctypes.c_float(lr),
+                              ctypes.c_uint64(sr_seed & 0xFFFFFFFFFFFFFFFF), _p(out))
+    return out

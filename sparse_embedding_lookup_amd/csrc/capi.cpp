@@ -209,21 +209,25 @@ int32_t ctr_embbag_bwd(const float* grad, int64_t grad_stride_b, int64_t grad_st
   return hip_status(ctr::launch_embbag_bwd(grad, grad_stride_b, grad_stride_t, offsets, batch,
                                            num_tables, dim, nnz, perm, inverse,
                                            reinterpret_cast<const int4*>(sorted_src), num_unique,
-                                           row_grads, nullptr, 0, 0, nullptr, 0.f, workspace,
+                                           row_grads, nullptr, 0, 0, nullptr, 0.f, 0, workspace,
                                            (hipStream_t)stream),
                     "ctr_embbag_bwd");
 }
 
-int32_t ctr_embbag_bwd_sgd(const float* grad, int64_t grad_stride_b, int64_t grad_stride_t,
-                           const int64_t* offsets, int64_t batch, int32_t num_tables,
-                           int64_t nnz, const int32_t* sorted_src, const int32_t* num_unique,
-                           void* table, int32_t dtype, int64_t total_rows, int32_t dim,
-                           const int64_t* uniq, float lr, float* row_grads, void* workspace,
-                           size_t* workspace_bytes, void* stream) {
+static int32_t embbag_bwd_sgd_common(const float* grad, int64_t grad_stride_b,
+                                     int64_t grad_stride_t, const int64_t* offsets,
+                                     int64_t batch, int32_t num_tables, int64_t nnz,
+                                     const int32_t* sorted_src, const int32_t* num_unique,
+                                     void* table, int32_t dtype, int64_t total_rows, int32_t dim,
+                                     const int64_t* uniq, float lr, float* row_grads,
+                                     void* workspace, size_t* workspace_bytes, bool stochastic,
+                                     uint64_t seed, void* stream, const char* name) {
   g_msg[0] = 0;
   if (!workspace_bytes) return fail(CTR_ERR_INVALID_ARGUMENT, "workspace_bytes is NULL");
   int32_t st = check_table(table, dtype, total_rows, dim);
   if (st) return st;
+  if (stochastic && dtype != CTR_BF16)
+    return fail(CTR_ERR_UNSUPPORTED, "stochastic rounding needs a CTR_BF16 table");
   if (dim > 1024) return fail(CTR_ERR_UNSUPPORTED, "dim %d above 1024", dim);
   if (nnz < 0 || nnz > kMaxElems) return fail(CTR_ERR_INVALID_ARGUMENT, "bad nnz");
   if (num_tables < 1) return fail(CTR_ERR_INVALID_ARGUMENT, "num_tables must be >= 1");
@@ -253,17 +257,46 @@ int32_t ctr_embbag_bwd_sgd(const float* grad, int64_t grad_stride_b, int64_t gra
   return hip_status(ctr::launch_embbag_bwd(grad, grad_stride_b, grad_stride_t, offsets, batch,
                                            num_tables, dim, nnz, nullptr, nullptr,
                                            reinterpret_cast<const int4*>(sorted_src), num_unique,
-                                           row_grads, table, dtype == CTR_BF16 ? 2 : 1,
-                                           total_rows, uniq, lr, workspace, (hipStream_t)stream),
-                    "ctr_embbag_bwd_sgd");
+                                           row_grads, table,
+                                           dtype == CTR_BF16 ? (stochastic ? 3 : 2) : 1,
+                                           total_rows, uniq, lr, seed, workspace,
+                                           (hipStream_t)stream),
+                    name);
 }
 
-int32_t ctr_sparse_sgd(void* table, int32_t dtype, int64_t total_rows, int32_t dim,
-                       const int64_t* uniq, const int32_t* num_unique, int64_t capacity,
-                       const float* row_grads, float lr, void* stream) {
+int32_t ctr_embbag_bwd_sgd(const float* grad, int64_t grad_stride_b, int64_t grad_stride_t,
+                           const int64_t* offsets, int64_t batch, int32_t num_tables,
+                           int64_t nnz, const int32_t* sorted_src, const int32_t* num_unique,
+                           void* table, int32_t dtype, int64_t total_rows, int32_t dim,
+                           const int64_t* uniq, float lr, float* row_grads, void* workspace,
+                           size_t* workspace_bytes, void* stream) {
+  return embbag_bwd_sgd_common(grad, grad_stride_b, grad_stride_t, offsets, batch, num_tables,
+                               nnz, sorted_src, num_unique, table, dtype, total_rows, dim, uniq,
+                               lr, row_grads, workspace, workspace_bytes, false, 0, stream,
+                               "ctr_embbag_bwd_sgd");
+}
+
+int32_t ctr_embbag_bwd_sgd_sr(const float* grad, int64_t grad_stride_b, int64_t grad_stride_t,
+                              const int64_t* offsets, int64_t batch, int32_t num_tables,
+                              int64_t nnz, const int32_t* sorted_src, const int32_t* num_unique,
+                              void* table, int32_t dtype, int64_t total_rows, int32_t dim,
+                              const int64_t* uniq, float lr, uint64_t seed, float* row_grads,
+                              void* workspace, size_t* workspace_bytes, void* stream) {
+  return embbag_bwd_sgd_common(grad, grad_stride_b, grad_stride_t, offsets, batch, num_tables,
+                               nnz, sorted_src, num_unique, table, dtype, total_rows, dim, uniq,
+                               lr, row_grads, workspace, workspace_bytes, true, seed, stream,
+                               "ctr_embbag_bwd_sgd_sr");
+}
+
+static int32_t sparse_sgd_common(void* table, int32_t dtype, int64_t total_rows, int32_t dim,
+                                 const int64_t* uniq, const int32_t* num_unique,
+                                 int64_t capacity, const float* row_grads, float lr,
+                                 bool stochastic, uint64_t seed, void* stream, const char* name) {
   g_msg[0] = 0;
   int32_t st = check_table(table, dtype, total_rows, dim);
   if (st) return st;
+  if (stochastic && dtype != CTR_BF16)
+    return fail(CTR_ERR_UNSUPPORTED, "stochastic rounding needs a CTR_BF16 table");
   if (capacity < 0 || capacity > kMaxElems) return fail(CTR_ERR_INVALID_ARGUMENT, "bad capacity");
   if (capacity > 0 && (!uniq || !num_unique || !row_grads))
     return fail(CTR_ERR_INVALID_ARGUMENT, "uniq, num_unique and row_grads are required");
@@ -271,9 +304,30 @@ int32_t ctr_sparse_sgd(void* table, int32_t dtype, int64_t total_rows, int32_t d
   if (row_grads && !aligned16(row_grads))
     return fail(CTR_ERR_UNSUPPORTED, "row_grads is not 16-byte aligned");
   return hip_status(ctr::launch_sparse_sgd(table, dtype == CTR_BF16, total_rows, dim, uniq,
-                                           num_unique, capacity, row_grads, lr,
+                                           num_unique, capacity, row_grads, lr, stochastic, seed,
                                            (hipStream_t)stream),
-                    "ctr_sparse_sgd");
+                    name);
+}
+
+int32_t ctr_sparse_sgd(void* table, int32_t dtype, int64_t total_rows, int32_t dim,
+                       const int64_t* uniq, const int32_t* num_unique, int64_t capacity,
+                       const float* row_grads, float lr, void* stream) {
+  return sparse_sgd_common(table, dtype, total_rows, dim, uniq, num_unique, capacity, row_grads,
+                           lr, false, 0, stream, "ctr_sparse_sgd");
+}
+
+uint64_t ctr_sr_step_seed(uint64_t base, int64_t k) {
+  uint64_t z = base + (uint64_t)(k + 1) * 0x9E3779B97F4A7C15ull;
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  return z ^ (z >> 31);
+}
+
+int32_t ctr_sparse_sgd_sr(void* table, int32_t dtype, int64_t total_rows, int32_t dim,
+                          const int64_t* uniq, const int32_t* num_unique, int64_t capacity,
+                          const float* row_grads, float lr, uint64_t seed, void* stream) {
+  return sparse_sgd_common(table, dtype, total_rows, dim, uniq, num_unique, capacity, row_grads,
+                           lr, true, seed, stream, "ctr_sparse_sgd_sr");
 }
 
 static int32_t check_interaction(const float* Z, int64_t batch, int32_t F, int32_t dim,

@@ -23,6 +23,37 @@ __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
 
 __device__ __forceinline__ float qnan() { return __uint_as_float(0x7FC00000u); }
 
+// One splitmix64 output from `state` (Steele, Lea, Flood, "Fast splittable pseudorandom
+// number generators", OOPSLA 2014): add the golden-ratio increment, then two
+// xor-shift-multiply rounds and a final xor-shift.
+__device__ __forceinline__ uint64_t splitmix64_out(uint64_t state) {
+  uint64_t z = state + 0x9E3779B97F4A7C15ull;
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  return z ^ (z >> 31);
+}
+
+// Random bits of a stochastically rounded update drawn with `seed`, for the four columns
+// c4 .. c4+3 (c4 a multiple of 4) of row key: one splitmix64 output from state
+// seed ^ (key*dim + c4); column c4 + e takes bits 16e .. 16e+15.
+__device__ __forceinline__ uint64_t sr_bits4(uint64_t seed, int64_t key, int64_t c4, int dim) {
+  return splitmix64_out(seed ^ (uint64_t)(key * (int64_t)dim + c4));
+}
+__device__ __forceinline__ uint32_t sr_take(uint64_t bits4, int e) {
+  return (uint32_t)(bits4 >> (16 * e)) & 0xFFFFu;
+}
+
+// binary32 -> bf16 with stochastic rounding ("DHEN" notes, 6.4 "Common Optimizations"):
+// keep the top half of the pattern and add one unit in the last place (away from zero: the
+// pattern is sign-magnitude) when r is below the dropped low half, i.e. with probability
+// (|x| - |lo|) / (|hi| - |lo|).  Exact values and infinities are kept; the largest finite
+// value rounding up gives infinity; NaN becomes a quiet NaN.
+__device__ __forceinline__ uint32_t f32_to_bf16_sr(float x, uint32_t r) {
+  const uint32_t b = __float_as_uint(x);
+  if ((b & 0x7FFFFFFFu) > 0x7F800000u) return 0x7FC0u;
+  return (b >> 16) + (r < (b & 0xFFFFu) ? 1u : 0u);
+}
+
 // Sixteen bytes of a row widened to fp32: 4 floats (fp32 rows) or 8 floats (bf16 rows).
 template <bool BF16>
 struct Vec;
@@ -100,7 +131,8 @@ hipError_t launch_gather_rows(const void* table, bool bf16, int64_t total_rows, 
                               float* out, hipStream_t s);
 hipError_t launch_sparse_sgd(void* table, bool bf16, int64_t total_rows, int dim,
                              const int64_t* uniq, const int32_t* num_unique, int64_t capacity,
-                             const float* g, float lr, hipStream_t s);
+                             const float* g, float lr, bool stochastic, uint64_t seed,
+                             hipStream_t s);
 hipError_t launch_init_table(void* table, bool bf16, int dim, int64_t row_begin,
                              int64_t rows, float scale, uint64_t seed, hipStream_t s);
 hipError_t launch_validate_csr(const void* idx, bool idx64, int64_t nnz, const int64_t* offsets,
@@ -114,7 +146,7 @@ hipError_t launch_embbag_bwd(const float* grad, int64_t sb, int64_t st, const in
                              const int32_t* perm, const int32_t* inverse, const int4* sorted_src,
                              const int32_t* num_unique, float* row_grads, void* table,
                              int sgd_mode, int64_t total_rows, const int64_t* uniq, float lr,
-                             void* workspace, hipStream_t s);
+                             uint64_t seed, void* workspace, hipStream_t s);
 
 // interaction.hip
 bool interaction_bf16_supported(int F, int dim);

@@ -333,12 +333,13 @@ __global__ __launch_bounds__(kThreads) void gather_rows_kernel(
   }
 }
 
-// W[uniq[u]] = round(W[uniq[u]] - lr * g[u]) for u < min(num_unique, capacity).
-template <bool BF16, int G, int VPL>
+// W[uniq[u]] = round(W[uniq[u]] - lr * g[u]) for u < min(num_unique, capacity); bf16 rounds
+// to nearest-even, or stochastically (SR) with the element's random bits from `seed`.
+template <bool BF16, bool SR, int G, int VPL>
 __global__ __launch_bounds__(kThreads) void sparse_sgd_kernel(
     char* __restrict__ table, int64_t total_rows, int64_t row_bytes, int vecs,
     const int64_t* __restrict__ uniq, const int32_t* __restrict__ num_unique, int64_t capacity,
-    const float* __restrict__ g, int64_t g_stride, float lr) {
+    const float* __restrict__ g, int64_t g_stride, float lr, uint64_t seed) {
   using V = Vec<BF16>;
   constexpr int E = V::kElems;
   const int lane = threadIdx.x & (G - 1);
@@ -368,11 +369,20 @@ __global__ __launch_bounds__(kThreads) void sparse_sgd_kernel(
 #pragma unroll
     for (int e = 0; e < E; ++e) nw[e] = __builtin_fmaf(-lr, gr[e], w.v[e]);
     if (BF16) {
+      uint32_t h[E];
+      uint64_t bits[2] = {0, 0};
+      if (SR) {
+        bits[0] = sr_bits4(seed, key, (int64_t)vi * E, vecs * E);
+        bits[1] = sr_bits4(seed, key, (int64_t)vi * E + 4, vecs * E);
+      }
+#pragma unroll
+      for (int e = 0; e < E; ++e)
+        h[e] = SR ? f32_to_bf16_sr(nw[e], sr_take(bits[e / 4], e % 4)) : f32_to_bf16_bits(nw[e]);
       uint4 q;
-      q.x = f32_to_bf16_bits(nw[0]) | (f32_to_bf16_bits(nw[1]) << 16);
-      q.y = f32_to_bf16_bits(nw[2]) | (f32_to_bf16_bits(nw[3]) << 16);
-      q.z = f32_to_bf16_bits(nw[4 % E]) | (f32_to_bf16_bits(nw[5 % E]) << 16);
-      q.w = f32_to_bf16_bits(nw[6 % E]) | (f32_to_bf16_bits(nw[7 % E]) << 16);
+      q.x = h[0] | (h[1] << 16);
+      q.y = h[2] | (h[3] << 16);
+      q.z = h[4 % E] | (h[5 % E] << 16);
+      q.w = h[6 % E] | (h[7 % E] << 16);
       *reinterpret_cast<uint4*>(wp) = q;
     } else {
       *reinterpret_cast<float4*>(wp) = make_float4(nw[0], nw[1], nw[2], nw[3]);
@@ -384,10 +394,7 @@ __global__ __launch_bounds__(kThreads) void sparse_sgd_kernel(
 // splitmix64 output from state seed ^ (r*dim + c) (Steele, Lea, Flood, OOPSLA 2014).
 __device__ __forceinline__ float hash_value(uint64_t seed, int64_t r, int64_t c, int dim,
                                             float scale) {
-  uint64_t z = (seed ^ (uint64_t)(r * (int64_t)dim + c)) + 0x9E3779B97F4A7C15ull;
-  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
-  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
-  z ^= z >> 31;
+  const uint64_t z = splitmix64_out(seed ^ (uint64_t)(r * (int64_t)dim + c));
   const float u = (float)(uint32_t)(z >> 40) * (1.0f / 16777216.0f);
   const float sgn = 2.0f * u - 1.0f;           // exact in binary32
   return __fmul_rn(sgn, scale);
@@ -554,7 +561,8 @@ hipError_t launch_gather_rows(const void* table, bool bf16, int64_t total_rows, 
 
 hipError_t launch_sparse_sgd(void* table, bool bf16, int64_t total_rows, int dim,
                              const int64_t* uniq, const int32_t* num_unique, int64_t capacity,
-                             const float* g, float lr, hipStream_t s) {
+                             const float* g, float lr, bool stochastic, uint64_t seed,
+                             hipStream_t s) {
   if (capacity == 0) return hipSuccess;
   const int E = bf16 ? 8 : 4;
   const int vecs = dim / E;
@@ -563,12 +571,15 @@ hipError_t launch_sparse_sgd(void* table, bool bf16, int64_t total_rows, int dim
   char* tb = static_cast<char*>(table);
   CTR_DISPATCH_G_VPL(rg.G, rg.VPL, {
     const int64_t blocks = (capacity + (kThreads / G) - 1) / (kThreads / G);
-    if (bf16)
-      sparse_sgd_kernel<true, G, VPL><<<(unsigned)blocks, kThreads, 0, s>>>(
-          tb, total_rows, row_bytes, vecs, uniq, num_unique, capacity, g, dim, lr);
+    if (bf16 && stochastic)
+      sparse_sgd_kernel<true, true, G, VPL><<<(unsigned)blocks, kThreads, 0, s>>>(
+          tb, total_rows, row_bytes, vecs, uniq, num_unique, capacity, g, dim, lr, seed);
+    else if (bf16)
+      sparse_sgd_kernel<true, false, G, VPL><<<(unsigned)blocks, kThreads, 0, s>>>(
+          tb, total_rows, row_bytes, vecs, uniq, num_unique, capacity, g, dim, lr, seed);
     else
-      sparse_sgd_kernel<false, G, VPL><<<(unsigned)blocks, kThreads, 0, s>>>(
-          tb, total_rows, row_bytes, vecs, uniq, num_unique, capacity, g, dim, lr);
+      sparse_sgd_kernel<false, false, G, VPL><<<(unsigned)blocks, kThreads, 0, s>>>(
+          tb, total_rows, row_bytes, vecs, uniq, num_unique, capacity, g, dim, lr, seed);
   });
   return hipGetLastError();
 }

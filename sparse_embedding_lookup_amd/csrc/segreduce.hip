@@ -105,16 +105,36 @@ __device__ __forceinline__ int32_t key_after(const Src& S, int64_t q, int64_t n)
 }
 
 // Where a finished row gradient goes besides row_grads: nowhere (MODE 0), or straight into
-// the sparse SGD update W[uniq[u]] -= lr * g[u] of an fp32 (MODE 1) or bf16 (MODE 2) table,
-// with the same arithmetic as the stand-alone update (one fused multiply-add, then
-// nearest-even for bf16).
+// the sparse SGD update W[uniq[u]] -= lr * g[u] of an fp32 (MODE 1) or bf16 table, rounded
+// to nearest-even (MODE 2) or stochastically with the element's bits from `seed` (MODE 3),
+// with the same arithmetic as the stand-alone update (one fused multiply-add, then the
+// rounding).
 struct SgdTarget {
   char* table;
   int64_t total_rows;
   int64_t row_bytes;
   const int64_t* uniq;
   float lr;
+  uint64_t seed;
 };
+
+// Four bf16 table values (columns c..c+3 of row key) after W - lr * g.
+template <int MODE>
+__device__ __forceinline__ uint2 bf16_updated(const SgdTarget& sgd, int64_t key, int c,
+                                              float g0, float g1, float g2, float g3,
+                                              uint2 w) {
+  const float n[4] = {__builtin_fmaf(-sgd.lr, g0, bf16_lo(w.x)),
+                      __builtin_fmaf(-sgd.lr, g1, bf16_hi(w.x)),
+                      __builtin_fmaf(-sgd.lr, g2, bf16_lo(w.y)),
+                      __builtin_fmaf(-sgd.lr, g3, bf16_hi(w.y))};
+  uint32_t h[4];
+  uint64_t bits = 0;
+  if constexpr (MODE == 3) bits = sr_bits4(sgd.seed, key, c, (int)(sgd.row_bytes >> 1));
+#pragma unroll
+  for (int e = 0; e < 4; ++e)
+    h[e] = MODE == 3 ? f32_to_bf16_sr(n[e], sr_take(bits, e)) : f32_to_bf16_bits(n[e]);
+  return make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
+}
 
 template <int G, int VPL>
 struct SegSmem {
@@ -130,13 +150,13 @@ struct SegSmem {
 // Table-row part of one lane (4 columns) and its update W <- W - lr * g: one fused
 // multiply-add in fp32, then a plain store (fp32) or nearest-even to bf16.
 template <int MODE>
-using WVec = typename std::conditional<MODE == 2, uint2, float4>::type;
+using WVec = typename std::conditional<(MODE >= 2), uint2, float4>::type;
 
 template <int MODE>
 __device__ __forceinline__ WVec<MODE> load_wvec(const SgdTarget& sgd, int64_t key, int c,
                                                 bool ok) {
   const char* wrow = sgd.table + key * sgd.row_bytes;
-  if constexpr (MODE == 2)
+  if constexpr (MODE >= 2)
     return ok ? *reinterpret_cast<const uint2*>(wrow + (int64_t)c * 2) : make_uint2(0u, 0u);
   else
     return ok ? *reinterpret_cast<const float4*>(wrow + (int64_t)c * 4)
@@ -151,14 +171,9 @@ __device__ __forceinline__ void store_updated(const SgdTarget& sgd, int64_t key,
     *reinterpret_cast<float4*>(wrow + (int64_t)c * 4) =
         make_float4(__builtin_fmaf(-sgd.lr, g.x, x.x), __builtin_fmaf(-sgd.lr, g.y, x.y),
                     __builtin_fmaf(-sgd.lr, g.z, x.z), __builtin_fmaf(-sgd.lr, g.w, x.w));
-  } else if constexpr (MODE == 2) {
-    const float n0 = __builtin_fmaf(-sgd.lr, g.x, bf16_lo(x.x));
-    const float n1 = __builtin_fmaf(-sgd.lr, g.y, bf16_hi(x.x));
-    const float n2 = __builtin_fmaf(-sgd.lr, g.z, bf16_lo(x.y));
-    const float n3 = __builtin_fmaf(-sgd.lr, g.w, bf16_hi(x.y));
+  } else if constexpr (MODE >= 2) {
     *reinterpret_cast<uint2*>(wrow + (int64_t)c * 2) =
-        make_uint2(f32_to_bf16_bits(n0) | (f32_to_bf16_bits(n1) << 16),
-                   f32_to_bf16_bits(n2) | (f32_to_bf16_bits(n3) << 16));
+        bf16_updated<MODE>(sgd, key, c, g.x, g.y, g.z, g.w, x);
   }
 }
 
@@ -340,13 +355,8 @@ __device__ __forceinline__ void reduce_chunk(
                             __builtin_fmaf(-sgd.lr, r.v[a][3], w.w));
         } else {
           uint2* wp = reinterpret_cast<uint2*>(wrow + (int64_t)c * 2);
-          const uint2 w = *wp;
-          const float n0 = __builtin_fmaf(-sgd.lr, r.v[a][0], bf16_lo(w.x));
-          const float n1 = __builtin_fmaf(-sgd.lr, r.v[a][1], bf16_hi(w.x));
-          const float n2 = __builtin_fmaf(-sgd.lr, r.v[a][2], bf16_lo(w.y));
-          const float n3 = __builtin_fmaf(-sgd.lr, r.v[a][3], bf16_hi(w.y));
-          *wp = make_uint2(f32_to_bf16_bits(n0) | (f32_to_bf16_bits(n1) << 16),
-                           f32_to_bf16_bits(n2) | (f32_to_bf16_bits(n3) << 16));
+          *wp = bf16_updated<MODE>(sgd, key, c, r.v[a][0], r.v[a][1], r.v[a][2], r.v[a][3],
+                                   *wp);
         }
       }
     }
@@ -672,7 +682,7 @@ hipError_t launch_embbag_bwd(const float* grad, int64_t sb, int64_t st, const in
                              const int32_t* perm, const int32_t* inverse, const int4* sorted_src,
                              const int32_t* num_unique, float* row_grads, void* table,
                              int sgd_mode, int64_t total_rows, const int64_t* uniq, float lr,
-                             void* workspace, hipStream_t s) {
+                             uint64_t seed, void* workspace, hipStream_t s) {
   (void)num_unique;
   if (nnz == 0) return hipSuccess;
   BwdWs w = carve(workspace, nnz, dim);
@@ -691,11 +701,13 @@ hipError_t launch_embbag_bwd(const float* grad, int64_t sb, int64_t st, const in
 
   L0Source s0{src, grad, sb, st, batch, num_bags};
   SgdTarget sgd{static_cast<char*>(table), total_rows,
-                (int64_t)dim * (sgd_mode == 2 ? 2 : 4), uniq, lr};
+                (int64_t)dim * (sgd_mode >= 2 ? 2 : 4), uniq, lr, seed};
   if (sgd_mode == 1)
     segreduce_levels<1>(s0, nnz, dim, row_grads, sgd, w, s);
   else if (sgd_mode == 2)
     segreduce_levels<2>(s0, nnz, dim, row_grads, sgd, w, s);
+  else if (sgd_mode == 3)
+    segreduce_levels<3>(s0, nnz, dim, row_grads, sgd, w, s);
   else
     segreduce_levels<0>(s0, nnz, dim, row_grads, sgd, w, s);
   return hipGetLastError();

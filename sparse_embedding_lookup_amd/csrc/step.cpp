@@ -101,18 +101,24 @@ int32_t interaction_part(const ctr_step_t* d, hipStream_t s) {
 }
 
 // The backward with the SGD update of the touched rows.
-int32_t sgd_part(const ctr_step_t* d, int set, hipStream_t s) {
+int32_t sgd_part(const ctr_step_t* d, int set, int64_t k, hipStream_t s) {
   const int64_t F = (int64_t)d->num_tables + 1;
   size_t wsb = d->ws_bwd_bytes;
-  if (d->kind == CTR_STEP_POOLED_INTERACTION)
-    return ctr_embbag_bwd_sgd(d->dZ + d->dim, F * d->dim, d->dim, d->offsets, d->batch,
-                              d->num_tables, d->nnz, d->sorted_src[set], d->num_unique[set],
-                              d->table, d->dtype, d->total_rows, d->dim, d->uniq[set], d->lr,
-                              d->row_grads, d->ws_bwd, &wsb, s);
-  return ctr_embbag_bwd_sgd(d->dout, d->dim, 0, d->offsets, d->nnz, 1, d->nnz,
-                            d->sorted_src[set], d->num_unique[set], d->table, d->dtype,
-                            d->total_rows, d->dim, d->uniq[set], d->lr, d->row_grads, d->ws_bwd,
-                            &wsb, s);
+  const bool pooled = d->kind == CTR_STEP_POOLED_INTERACTION;
+  const float* grad = pooled ? d->dZ + d->dim : d->dout;
+  const int64_t sb = pooled ? F * d->dim : d->dim;
+  const int64_t st = pooled ? d->dim : 0;
+  const int64_t batch = pooled ? d->batch : d->nnz;
+  const int32_t tables = pooled ? d->num_tables : 1;
+  if (d->rounding == CTR_ROUND_STOCHASTIC)
+    return ctr_embbag_bwd_sgd_sr(grad, sb, st, d->offsets, batch, tables, d->nnz,
+                                 d->sorted_src[set], d->num_unique[set], d->table, d->dtype,
+                                 d->total_rows, d->dim, d->uniq[set], d->lr,
+                                 ctr_sr_step_seed(d->sr_seed, k), d->row_grads, d->ws_bwd, &wsb,
+                                 s);
+  return ctr_embbag_bwd_sgd(grad, sb, st, d->offsets, batch, tables, d->nnz, d->sorted_src[set],
+                            d->num_unique[set], d->table, d->dtype, d->total_rows, d->dim,
+                            d->uniq[set], d->lr, d->row_grads, d->ws_bwd, &wsb, s);
 }
 
 }  // namespace
@@ -134,6 +140,8 @@ int32_t ctr_step_run(const ctr_step_t* d, int64_t k, int32_t schedule, void* mai
   if (d->kind != CTR_STEP_POOLED_INTERACTION && d->kind != CTR_STEP_BATCH_MATRIX)
     return invalid("unknown step kind");
   if (k < 0) return invalid("step index k < 0");
+  if (d->rounding != CTR_ROUND_NEAREST && d->rounding != CTR_ROUND_STOCHASTIC)
+    return invalid("unknown rounding");
   if (schedule < CTR_SCHEDULE_SERIAL || schedule > CTR_SCHEDULE_PIPELINED_OVERLAP)
     return invalid("unknown schedule");
   if (side_stream && (!fork_event || !join_event))
@@ -158,7 +166,7 @@ int32_t ctr_step_run(const ctr_step_t* d, int64_t k, int32_t schedule, void* mai
     CTR_TRY(forward_part(d, 0, s, mark_begin, mark_end));
     CTR_TRY(interaction_part(d, s));
     if (fork) CTR_TRY(wait(s, join_event));
-    return sgd_part(d, 0, s);
+    return sgd_part(d, 0, k, s);
   }
   const int cur = (int)(k & 1), nxt = cur ^ 1;
   if (schedule == CTR_SCHEDULE_PIPELINED_OVERLAP) {
@@ -173,7 +181,7 @@ int32_t ctr_step_run(const ctr_step_t* d, int64_t k, int32_t schedule, void* mai
     CTR_TRY(wait(side, fork_event));
     CTR_TRY(unique_into(d, nxt, side));
     CTR_TRY(record(join_event, side));
-    CTR_TRY(sgd_part(d, cur, s));
+    CTR_TRY(sgd_part(d, cur, k, s));
     return record(fork_event, s);
   }
   // pipelined: batch k uses set k % 2 (filled during step k-1, or by ctr_step_unique before
@@ -187,7 +195,7 @@ int32_t ctr_step_run(const ctr_step_t* d, int64_t k, int32_t schedule, void* mai
   CTR_TRY(record(join_event, side));
   if (early) CTR_TRY(forward_part(d, cur, s, mark_begin, mark_end));
   CTR_TRY(interaction_part(d, s));
-  CTR_TRY(sgd_part(d, cur, s));
+  CTR_TRY(sgd_part(d, cur, k, s));
   return wait(s, join_event);
 }
 

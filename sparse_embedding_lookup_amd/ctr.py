@@ -24,12 +24,13 @@ EXPORTED = [
     "ctr_embbag_fwd", "ctr_embbag_bwd", "ctr_embbag_bwd_sgd", "ctr_sparse_sgd",
     "ctr_dot_interaction_fwd",
     "ctr_dot_interaction_bwd", "ctr_init_table_hash", "ctr_validate_csr", "ctr_step_run",
-    "ctr_step_unique",
+    "ctr_step_unique", "ctr_embbag_bwd_sgd_sr", "ctr_sparse_sgd_sr", "ctr_sr_step_seed",
 ]
 
 CTR_STEP_POOLED_INTERACTION, CTR_STEP_BATCH_MATRIX = 0, 1
 CTR_SCHEDULE_SERIAL, CTR_SCHEDULE_PIPELINED, CTR_SCHEDULE_PIPELINED_EARLY = 0, 1, 2
 CTR_SCHEDULE_PIPELINED_OVERLAP = 3
+CTR_ROUND_NEAREST, CTR_ROUND_STOCHASTIC = 0, 1
 
 
 class CtrStep(ctypes.Structure):
@@ -45,7 +46,8 @@ class CtrStep(ctypes.Structure):
                 ("ws_unique_bytes", ctypes.c_size_t), ("ws_bwd", _P),
                 ("ws_bwd_bytes", ctypes.c_size_t), ("uniq", _P * 2), ("inverse", _P * 2),
                 ("num_unique", _P * 2), ("perm", _P * 2), ("seg_offsets", _P * 2),
-                ("sorted_src", _P * 2)]
+                ("sorted_src", _P * 2), ("rounding", ctypes.c_int32),
+                ("sr_seed", ctypes.c_uint64)]
 
 _lib = None
 
@@ -83,6 +85,10 @@ def load() -> ctypes.CDLL:
         "ctr_embbag_bwd_sgd": (i32, [P, i64, i64, P, i64, i32, i64, P, P, P, i32, i64, i32, P,
                                      f32, P, P, PS, P]),
         "ctr_sparse_sgd": (i32, [P, i32, i64, i32, P, P, i64, P, f32, P]),
+        "ctr_embbag_bwd_sgd_sr": (i32, [P, i64, i64, P, i64, i32, i64, P, P, P, i32, i64, i32,
+                                        P, f32, u64, P, P, PS, P]),
+        "ctr_sparse_sgd_sr": (i32, [P, i32, i64, i32, P, P, i64, P, f32, u64, P]),
+        "ctr_sr_step_seed": (u64, [u64, i64]),
         "ctr_dot_interaction_fwd": (i32, [P, i64, i32, i32, i32, P, i64, P]),
         "ctr_dot_interaction_bwd": (i32, [P, P, i64, i64, i32, i32, i32, P, P]),
         "ctr_init_table_hash": (i32, [P, i32, i32, P, i32, u64, P]),
@@ -273,6 +279,41 @@ def ctr_embbag_bwd_sgd(grad: torch.Tensor, grad_stride_b: int, grad_stride_t: in
             _ptr(sorted_src), _ptr(num_unique), _ptr(table), _dtype_code(table), total_rows, dim,
             _ptr(uniq), ctypes.c_float(lr), _ptr(row_grads), _ptr(workspace), ctypes.byref(wsb))
     return _run("ctr_embbag_bwd_sgd", args, stream, prepare, row_grads)
+
+
+def ctr_embbag_bwd_sgd_sr(grad: torch.Tensor, grad_stride_b: int, grad_stride_t: int,
+                          offsets: torch.Tensor, batch: int, num_tables: int, nnz: int,
+                          sorted_src: torch.Tensor, num_unique: torch.Tensor,
+                          table: torch.Tensor, uniq: torch.Tensor, lr: float, seed: int,
+                          row_grads: Optional[torch.Tensor] = None,
+                          workspace: Optional[torch.Tensor] = None, stream=None,
+                          prepare: bool = False):
+    """ctr_embbag_bwd_sgd with stochastic rounding of a bf16 table (random bits from seed)."""
+    total_rows, dim = table.shape
+    if workspace is None:
+        workspace = _workspace(embbag_bwd_workspace_bytes(nnz, dim), grad.device)
+    wsb = ctypes.c_size_t(workspace.numel())
+    args = (_ptr(grad), grad_stride_b, grad_stride_t, _ptr(offsets), batch, num_tables, nnz,
+            _ptr(sorted_src), _ptr(num_unique), _ptr(table), _dtype_code(table), total_rows, dim,
+            _ptr(uniq), ctypes.c_float(lr), ctypes.c_uint64(seed & 0xFFFFFFFFFFFFFFFF),
+            _ptr(row_grads), _ptr(workspace), ctypes.byref(wsb))
+    return _run("ctr_embbag_bwd_sgd_sr", args, stream, prepare, row_grads)
+
+
+def ctr_sparse_sgd_sr(table: torch.Tensor, uniq: torch.Tensor, num_unique: torch.Tensor,
+                      capacity: int, row_grads: torch.Tensor, lr: float, seed: int, stream=None,
+                      prepare: bool = False):
+    """ctr_sparse_sgd with stochastic rounding of a bf16 table (random bits from seed)."""
+    total_rows, dim = table.shape
+    args = (_ptr(table), _dtype_code(table), total_rows, dim, _ptr(uniq), _ptr(num_unique),
+            capacity, _ptr(row_grads), ctypes.c_float(lr),
+            ctypes.c_uint64(seed & 0xFFFFFFFFFFFFFFFF))
+    return _run("ctr_sparse_sgd_sr", args, stream, prepare)
+
+
+def ctr_sr_step_seed(base: int, k: int) -> int:
+    """Seed of the k-th stochastically rounded update of a run seeded with base."""
+    return int(load().ctr_sr_step_seed(base & 0xFFFFFFFFFFFFFFFF, k))
 
 
 def ctr_sparse_sgd(table: torch.Tensor, uniq: torch.Tensor, num_unique: torch.Tensor,

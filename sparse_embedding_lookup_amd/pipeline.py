@@ -28,16 +28,28 @@ def _dev(a: np.ndarray, device) -> torch.Tensor:
     return torch.from_numpy(np.ascontiguousarray(a)).to(device)
 
 
+SR_SEED = 0x5EED_0000_5EED_0005   # base seed of the stochastic-rounding bits
+
+
 class FrontEnd:
     """Device state for one workload: the tables, the batch and every buffer of the path."""
 
     def __init__(self, w: Workload, device="cuda", table: Optional[torch.Tensor] = None,
-                 fused: bool = True, keep_grads: bool = False, pipelined: bool = False):
+                 fused: bool = True, keep_grads: bool = False, pipelined: bool = False,
+                 rounding: str = "nearest", sr_seed: int = SR_SEED):
         """fused: the backward applies the sparse SGD as each row gradient completes
         (ctr_embbag_bwd_sgd); otherwise ctr_embbag_bwd then ctr_sparse_sgd.  keep_grads: also
         keep the per-row gradients in self.row_grads (always kept when not fused).
         pipelined: the unique outputs are double-buffered so that step_pipelined() can
-        deduplicate the next batch's IDs while the current batch trains."""
+        deduplicate the next batch's IDs while the current batch trains.
+        rounding: "nearest", or "stochastic" (bf16 tables): the k-th update of the run (the
+        native step k, or the k-th SGD stage run from Python) draws its rounding bits with
+        seed ctr_sr_step_seed(sr_seed, k)."""
+        assert rounding in ("nearest", "stochastic")
+        assert rounding == "nearest" or w.dtype == "bf16", "stochastic rounding: bf16 tables"
+        self.rounding = rounding
+        self.sr_seed = sr_seed
+        self._sr_k = 0
         self.w = w
         self.pipelined = pipelined
         self.fused = fused
@@ -172,9 +184,30 @@ class FrontEnd:
         self._c_embbag_bwd()
 
     def _sparse_sgd(self):
+        if self.rounding == "stochastic":
+            ctr.ctr_sparse_sgd_sr(self.table, self.uniq, self.num_unique, self.nnz,
+                                  self.row_grads, self.w.lr, self._sr_seed_next())
+            return
         self._c_sparse_sgd()
 
+    def _sr_seed_next(self) -> int:
+        seed = ctr.ctr_sr_step_seed(self.sr_seed, self._sr_k)
+        self._sr_k += 1
+        return seed
+
     def _embbag_bwd_sgd(self):
+        if self.rounding == "stochastic":      # a fresh seed per update: marshalled per call
+            w = self.w
+            d = w.dim
+            if w.interaction:
+                grad, sb, st, B, T = self.dZ[:, 1:, :], w.F * d, d, w.batch, w.num_tables
+            else:
+                grad, sb, st, B, T = self.dout, d, 0, self.nnz, 1
+            ctr.ctr_embbag_bwd_sgd_sr(grad, sb, st, self.offsets, B, T, self.nnz,
+                                      self.sorted_src, self.num_unique, self.table, self.uniq,
+                                      w.lr, self._sr_seed_next(), row_grads=self.row_grads,
+                                      workspace=self.ws_bwd)
+            return
         self._c_embbag_bwd_sgd()
 
     def stages(self):
@@ -353,6 +386,9 @@ class FrontEnd:
         d.row_base, d.key_modulus = P(self.row_base), w.key_modulus
         d.table, d.dtype, d.compute = P(self.table), ctr._dtype_code(self.table), self.compute
         d.total_rows, d.lr = w.total_rows, w.lr
+        d.rounding = (ctr.CTR_ROUND_STOCHASTIC if self.rounding == "stochastic"
+                      else ctr.CTR_ROUND_NEAREST)
+        d.sr_seed = self.sr_seed
         if w.interaction:
             d.Z, d.R, d.dR, d.dZ = P(self.Z), P(self.R), P(self.dR), P(self.dZ)
         else:

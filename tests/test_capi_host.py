@@ -153,6 +153,27 @@ def test_sgd_gather_init_validate_bad_args():
         ctr.CTR_ERR_INVALID_ARGUMENT
 
 
+def test_stochastic_rounding_entry_points_bad_args():
+    lib = _lib()
+    s0 = ctypes.c_uint64(7)
+    # fp32 tables have no stochastic rounding
+    st = lib.ctr_sparse_sgd_sr(FAKE, ctr.CTR_F32, 100, 16, FAKE, FAKE, 10, FAKE,
+                               ctypes.c_float(0.01), s0, None)
+    assert st == ctr.CTR_ERR_UNSUPPORTED and b"BF16" in lib.ctr_last_error()
+    assert lib.ctr_sparse_sgd_sr(FAKE, ctr.CTR_BF16, 100, 16, FAKE, FAKE, 10, FAKE,
+                                 ctypes.c_float(float("inf")), s0, None) == \
+        ctr.CTR_ERR_INVALID_ARGUMENT
+    wsb = ctypes.c_size_t(0)
+    st = lib.ctr_embbag_bwd_sgd_sr(FAKE, 64, 0, FAKE, 10, 1, 100, FAKE, FAKE, FAKE, ctr.CTR_F32,
+                                   1000, 16, FAKE, ctypes.c_float(0.01), s0, None, None,
+                                   ctypes.byref(wsb), None)
+    assert st == ctr.CTR_ERR_UNSUPPORTED
+    assert lib.ctr_embbag_bwd_sgd_sr(None, 64, 0, None, 10, 1, 100, None, None, FAKE,
+                                     ctr.CTR_BF16, 1000, 16, None, ctypes.c_float(0.01), s0,
+                                     None, None, ctypes.byref(wsb), None) == ctr.CTR_OK
+    assert wsb.value > 0                          # the workspace query of ctr_embbag_bwd
+
+
 def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
     monkeypatch.setattr(ctr, "LIB_PATH", str(tmp_path / "missing.so"))
     monkeypatch.setattr(ctr, "_lib", None)
