@@ -105,6 +105,52 @@ SINGLE_KERNEL = {
 }
 
 
+def time_variants(fe, w, K: int):
+    """The interaction variants on the workload's Z (after the timed steps), each call alone
+    bracketed by HIP events: the pair set with self-dots, forward and backward (P = F(F+1)/2),
+    and the FM sum by the squared-norm identity.  Algorithmic bytes: self forward
+    4BFd + 4B(d+P), backward 4B(d+P) + 8BFd; FM forward 4BFd + 4B, backward 8BFd + 4B."""
+    import torch
+    from sparse_embedding_lookup_amd import ctr
+
+    B, F, d = w.batch, w.F, w.dim
+    P = F * (F + 1) // 2
+    gen = torch.Generator(device="cuda").manual_seed(7)
+    dR = torch.randn((B, d + P), generator=gen, device="cuda")
+    dout = torch.randn((B,), generator=gen, device="cuda")
+    R = torch.empty((B, d + P), device="cuda")
+    dZ = torch.empty_like(fe.Z)
+    out = torch.empty((B,), device="cuda")
+    calls = {
+        "interaction_self_fwd": (ctr.ctr_dot_interaction_self_fwd(fe.Z, fe.compute, R, prepare=True),
+                                 4 * B * F * d + 4 * B * (d + P)),
+        "interaction_self_bwd": (ctr.ctr_dot_interaction_self_bwd(fe.Z, dR, fe.compute, dZ,
+                                                                  prepare=True),
+                                 4 * B * (d + P) + 8 * B * F * d),
+        "fm_fwd": (ctr.ctr_fm_interaction_fwd(fe.Z, out, prepare=True), 4 * B * F * d + 4 * B),
+        "fm_bwd": (ctr.ctr_fm_interaction_bwd(fe.Z, dout, dZ, prepare=True),
+                   8 * B * F * d + 4 * B),
+    }
+    res = {}
+    for name, (call, nbytes) in calls.items():
+        for _ in range(3):
+            call()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(K)]
+        for e0, e1 in ev:
+            e0.record()
+            call()
+            e1.record()
+        torch.cuda.synchronize()
+        ms = sum(a.elapsed_time(b) for a, b in ev) / K
+        gbps = nbytes / (ms * 1e-3) / 1e9
+        res[name] = {"ms": round(ms, 5), "bytes": nbytes, "gbps": round(gbps, 1),
+                     "frac": round(gbps / HBM_PEAK_GBPS, 4),
+                     "compute": "bf16" if fe.compute == ctr.CTR_BF16 and "fm" not in name
+                     else "f32"}
+    return res
+
+
 def measured_traffic(config: str, stage: str):
     """HBM bytes per launch of the stage's kernel from the committed rocprofv3 counter runs
     (FETCH_SIZE + WRITE_SIZE, each scaled by a plain copy of known size), or None when
@@ -234,6 +280,9 @@ def main():
     ap.add_argument("--rounding", default="nearest", choices=["nearest", "stochastic"],
                     help="bf16 tables: round the sparse update to nearest-even, or "
                          "stochastically (a fresh counter-based seed per step)")
+    ap.add_argument("--no-variants", dest="variants", action="store_false",
+                    help="skip timing the interaction variants (self-dots, FM sum) on the "
+                         "workload's Z")
     ap.add_argument("--compare-serial", action="store_true",
                     help="after a pipelined run, also time K serial steps (ms_per_step_serial)")
     args = ap.parse_args()
@@ -417,6 +466,8 @@ def main():
         torch.cuda.synchronize()
         ms_serial = (time.perf_counter() - t2) * 1e3 / K
 
+    variants = time_variants(fe, w, K) if (w.interaction and args.variants) else None
+
     step_bytes = sum(byts.values())
     value = w.nnz / (ms_step * 1e-3)
     achieved = byts[dominant] / (dom_ms * 1e-3) / 1e9
@@ -459,6 +510,7 @@ def main():
         "stage_ms": {k: round(v, 5) for k, v in stage_ms.items()},
         "stage_ms_cold": ({k: round(v, 5) for k, v in stage_ms_cold.items()}
                           if stage_ms_cold else None),
+        "variants": variants,
         "roofline": {"kernel": dominant, "bound": "hbm", "achieved": achieved,
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
                      "traffic": measured_traffic(

@@ -238,6 +238,35 @@ int32_t ctr_dot_interaction_bwd(const float* Z, const float* dR, int64_t dr_stri
                                 int32_t compute, float* dZ, void* stream);
 
 /*
+ * ctr_dot_interaction_self_fwd / _self_bwd -- the pair set with self-dots, [DHEN] 3.1 ("all
+ * inner products for i <= j"): as ctr_dot_interaction_fwd/bwd with the pairs F > i >= j >= 0
+ * in row-major lower-triangle order, P = F(F+1)/2:
+ *   R[b*r_stride + dim + i*(i+1)/2 + j]   = <Z[b, i, :], Z[b, j, :]>        i >= j
+ *   dZ[b, i, :] = sum over j != i of dP_(max,min) Z[b, j, :] + 2 dP_ii Z[b, i, :]
+ *                 + (i == 0 ? dR[b*dr_stride + 0 .. dim) : 0)
+ * Same arithmetic paths, limits and errors as the strict entry points; F >= 1.
+ */
+int32_t ctr_dot_interaction_self_fwd(const float* Z, int64_t batch, int32_t num_vectors,
+                                     int32_t dim, int32_t compute, float* R, int64_t r_stride,
+                                     void* stream);
+int32_t ctr_dot_interaction_self_bwd(const float* Z, const float* dR, int64_t dr_stride,
+                                     int64_t batch, int32_t num_vectors, int32_t dim,
+                                     int32_t compute, float* dZ, void* stream);
+
+/*
+ * ctr_fm_interaction_fwd / _bwd -- the sum of all pair dots by the squared-norm identity,
+ * [DHEN] Solution 2 (the FM trick), O(F * dim) per sample instead of O(F^2 * dim):
+ *   out[b] = sum over F > i > j >= 0 of <Z[b,i,:], Z[b,j,:]>
+ *          = 1/2 (||sum_i Z[b,i,:]||^2 - sum_i ||Z[b,i,:]||^2)      (fp32, the right side)
+ *   dZ[b, i, :] = dout[b] * (sum_j Z[b,j,:] - Z[b,i,:])
+ * Z, dZ: fp32 [batch, F, dim] contiguous; out, dout: fp32 [batch].  F >= 1.
+ */
+int32_t ctr_fm_interaction_fwd(const float* Z, int64_t batch, int32_t num_vectors, int32_t dim,
+                               float* out, void* stream);
+int32_t ctr_fm_interaction_bwd(const float* Z, const float* dout, int64_t batch,
+                               int32_t num_vectors, int32_t dim, float* dZ, void* stream);
+
+/*
  * ctr_init_table_hash -- fills a table with the counter-based values used by the seeded
  * workloads (input preparation, not part of the method): element (r, c) of table t is
  * x = fp32(2u - 1) * fp32(1/sqrt(rows_t)) with u = (splitmix64 output from state

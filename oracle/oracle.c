@@ -24,6 +24,8 @@
  *           section "Synchronous Architecture": only features present in the batch move.
  *   [DLRM]  "Meta DLRM" (upskillscore.com), section 02: the interaction is the dot product
  *           between all pairs of embedding vectors and the processed dense features.
+ *           Section 3.1 also names the pair set i <= j with self-dots; Solution 2 the FM
+ *           sum of all pair dots by the squared-norm identity.
  *           Section 6.4 "Common Optimizations": low-precision (FP16) embedding storage
  *           whose updates use stochastic rounding.
  * Readings where the pages are silent (sum pooling, strict i > j pair order, sum of
@@ -341,6 +343,117 @@ void orc_sparse_sgd(const float* data, uint64_t seed, const int64_t* row_base,
       new_rows[u * dim + c] = bf16 ? orc_round_bf16(x) : orc_round_f32(x);
       nmag[u * dim + c] = fabs(w) + l * gmag[u * dim + c];
     }
+}
+
+/* ------------------------------------------------------------------ interaction variants */
+/* [DHEN] 3.1: all inner products <x_i, x_j> for i <= j, self-dots included.  Pairs i >= j of
+ * z_0..z_{F-1} in row-major lower-triangle order, index i(i+1)/2 + j; R = [z_0 | pairs],
+ * P = F(F+1)/2.  Magnitudes as in orc_interaction_fwd. */
+void orc_interaction_self_fwd(const double* Z, const double* zmag, int64_t batch, int32_t F,
+                              int32_t dim, double* R, double* rmag) {
+  int64_t P = (int64_t)F * (F + 1) / 2, W = dim + P;
+#pragma omp parallel for schedule(static)
+  for (int64_t b = 0; b < batch; ++b) {
+    const double* z = Z + b * F * dim;
+    const double* zm = zmag ? zmag + b * F * dim : NULL;
+    for (int64_t c = 0; c < dim; ++c) {
+      R[b * W + c] = z[c];
+      rmag[b * W + c] = zm ? zm[c] : fabs(z[c]);
+    }
+    for (int64_t i = 0; i < F; ++i)
+      for (int64_t j = 0; j <= i; ++j) {
+        double s = 0.0, a = 0.0;
+        for (int64_t c = 0; c < dim; ++c) {
+          s += z[i * dim + c] * z[j * dim + c];
+          double mi = zm ? zm[i * dim + c] : fabs(z[i * dim + c]);
+          double mj = zm ? zm[j * dim + c] : fabs(z[j * dim + c]);
+          a += mi * mj;
+        }
+        R[b * W + dim + i * (i + 1) / 2 + j] = s;
+        rmag[b * W + dim + i * (i + 1) / 2 + j] = a;
+      }
+  }
+}
+
+/* Chain rule of the pair set with self-dots: dZ_i = sum over j != i of dP_(max,min) z_j
+ * + 2 dP_ii z_i (the derivative of <z_i, z_i>), plus the dense passthrough's gradient on
+ * dZ_0.  dR: [batch][dim + F(F+1)/2]. */
+void orc_interaction_self_bwd(const double* Z, const double* zmag, const double* dR,
+                              int64_t batch, int32_t F, int32_t dim, double* dZ, double* dmag) {
+  int64_t P = (int64_t)F * (F + 1) / 2, W = dim + P;
+#pragma omp parallel for schedule(static)
+  for (int64_t b = 0; b < batch; ++b) {
+    const double* z = Z + b * F * dim;
+    const double* zm = zmag ? zmag + b * F * dim : NULL;
+    const double* g = dR + b * W;
+    for (int64_t i = 0; i < F; ++i)
+      for (int64_t c = 0; c < dim; ++c) {
+        double s = 0.0, a = 0.0;
+        for (int64_t j = 0; j < F; ++j) {
+          int64_t hi = i > j ? i : j, lo = i > j ? j : i;
+          double gp = g[dim + hi * (hi + 1) / 2 + lo];
+          double k = (j == i) ? 2.0 : 1.0;
+          s += k * gp * z[j * dim + c];
+          a += k * fabs(gp) * (zm ? zm[j * dim + c] : fabs(z[j * dim + c]));
+        }
+        if (i == 0) {
+          s += g[c];
+          a += fabs(g[c]);
+        }
+        dZ[(b * F + i) * dim + c] = s;
+        dmag[(b * F + i) * dim + c] = a;
+      }
+  }
+}
+
+/* [DHEN] Solution 2, the FM sum: out[b] = sum over F > i > j >= 0 of <z_i, z_j>, written as
+ * that definition (O(F^2 d)).  The magnitude also counts 1/2 sum_i ||z_i||^2: the O(F d)
+ * squared-norm form 1/2 (||sum z_i||^2 - sum ||z_i||^2) cancels those self terms, and a
+ * forward-error bound of that evaluation scales with them. */
+void orc_fm_fwd(const double* Z, const double* zmag, int64_t batch, int32_t F, int32_t dim,
+                double* out, double* omag) {
+#pragma omp parallel for schedule(static)
+  for (int64_t b = 0; b < batch; ++b) {
+    const double* z = Z + b * F * dim;
+    const double* zm = zmag ? zmag + b * F * dim : NULL;
+    double s = 0.0, a = 0.0;
+    for (int64_t i = 0; i < F; ++i)
+      for (int64_t j = 0; j <= i; ++j)
+        for (int64_t c = 0; c < dim; ++c) {
+          double mi = zm ? zm[i * dim + c] : fabs(z[i * dim + c]);
+          double mj = zm ? zm[j * dim + c] : fabs(z[j * dim + c]);
+          if (j < i) {
+            s += z[i * dim + c] * z[j * dim + c];
+            a += mi * mj;
+          } else {
+            a += 0.5 * mi * mj;
+          }
+        }
+    out[b] = s;
+    omag[b] = a;
+  }
+}
+
+/* Its gradient: dZ_i = dout[b] * sum over j != i of z_j.  The magnitude sums |z_j| over all
+ * j (the O(F d) form computes sum_j z_j - z_i). */
+void orc_fm_bwd(const double* Z, const double* zmag, const double* dout, int64_t batch,
+                int32_t F, int32_t dim, double* dZ, double* dmag) {
+#pragma omp parallel for schedule(static)
+  for (int64_t b = 0; b < batch; ++b) {
+    const double* z = Z + b * F * dim;
+    const double* zm = zmag ? zmag + b * F * dim : NULL;
+    for (int64_t i = 0; i < F; ++i)
+      for (int64_t c = 0; c < dim; ++c) {
+        double s = 0.0, a = 0.0;
+        for (int64_t j = 0; j < F; ++j) {
+          double m = zm ? zm[j * dim + c] : fabs(z[j * dim + c]);
+          if (j != i) s += z[j * dim + c];
+          a += m;
+        }
+        dZ[(b * F + i) * dim + c] = dout[b] * s;
+        dmag[(b * F + i) * dim + c] = fabs(dout[b]) * a;
+      }
+  }
 }
 
 /* ------------------------------------------------------------------ stochastic rounding */

@@ -57,6 +57,10 @@ def _load():
         "orc_interaction_bwd": (None, [P, P, P, i64, i32, i32, P, P]),
         "orc_embbag_bwd": (None, [P, P, P, i64, i32, i32, P, i64, P, P]),
         "orc_sparse_sgd": (None, [P, u64, P, i32, i32, i32, P, i64, P, P, f32, P, P]),
+        "orc_interaction_self_fwd": (None, [P, P, i64, i32, i32, P, P]),
+        "orc_interaction_self_bwd": (None, [P, P, P, i64, i32, i32, P, P]),
+        "orc_fm_fwd": (None, [P, P, i64, i32, i32, P, P]),
+        "orc_fm_bwd": (None, [P, P, P, i64, i32, i32, P, P]),
         "orc_sr_bf16": (f64, [f64, ctypes.c_uint32]),
         "orc_sr_bits": (ctypes.c_uint32, [u64, i64, i64, i32]),
         "orc_sparse_sgd_sr": (None, [P, u64, P, i32, i32, P, i64, P, f32, u64, P]),
@@ -202,6 +206,50 @@ def interaction_bwd(Z, dR, zmag=None):
     dZ = np.empty((B, F, d), dtype=np.float64)
     dm = np.empty_like(dZ)
     _load().orc_interaction_bwd(_p(Z), _p(zm), _p(dR), B, F, d, _p(dZ), _p(dm))
+    return dZ, dm
+
+
+def interaction_self_fwd(Z, zmag=None):
+    """Pairs i >= j (self-dots included), P = F(F+1)/2: R = [dense | pairs], with magnitudes."""
+    Z = _c(Z, np.float64)
+    B, F, d = Z.shape
+    zm = None if zmag is None else _c(zmag, np.float64)
+    R = np.empty((B, d + F * (F + 1) // 2), dtype=np.float64)
+    Rm = np.empty_like(R)
+    _load().orc_interaction_self_fwd(_p(Z), _p(zm), B, F, d, _p(R), _p(Rm))
+    return R, Rm
+
+
+def interaction_self_bwd(Z, dR, zmag=None):
+    Z = _c(Z, np.float64)
+    B, F, d = Z.shape
+    dR = _c(dR, np.float64)
+    zm = None if zmag is None else _c(zmag, np.float64)
+    dZ = np.empty((B, F, d), dtype=np.float64)
+    dm = np.empty_like(dZ)
+    _load().orc_interaction_self_bwd(_p(Z), _p(zm), _p(dR), B, F, d, _p(dZ), _p(dm))
+    return dZ, dm
+
+
+def fm_fwd(Z, zmag=None):
+    """Sum of all pair dots per sample (the definition): returns (out [B], mag [B])."""
+    Z = _c(Z, np.float64)
+    B, F, d = Z.shape
+    zm = None if zmag is None else _c(zmag, np.float64)
+    out = np.empty(B, dtype=np.float64)
+    om = np.empty_like(out)
+    _load().orc_fm_fwd(_p(Z), _p(zm), B, F, d, _p(out), _p(om))
+    return out, om
+
+
+def fm_bwd(Z, dout, zmag=None):
+    Z = _c(Z, np.float64)
+    B, F, d = Z.shape
+    dout = _c(dout, np.float64)
+    zm = None if zmag is None else _c(zmag, np.float64)
+    dZ = np.empty((B, F, d), dtype=np.float64)
+    dm = np.empty_like(dZ)
+    _load().orc_fm_bwd(_p(Z), _p(zm), _p(dout), B, F, d, _p(dZ), _p(dm))
     return dZ, dm
 
 

@@ -331,45 +331,104 @@ int32_t ctr_sparse_sgd_sr(void* table, int32_t dtype, int64_t total_rows, int32_
 }
 
 static int32_t check_interaction(const float* Z, int64_t batch, int32_t F, int32_t dim,
-                                 int32_t compute, const float* out, int64_t stride) {
+                                 int32_t compute, bool self, const float* out, int64_t stride) {
   if (batch < 0 || batch > kMaxElems) return fail(CTR_ERR_INVALID_ARGUMENT, "bad batch");
-  if (F < 2) return fail(CTR_ERR_INVALID_ARGUMENT, "num_vectors must be >= 2 (got %d)", F);
+  if (F < (self ? 1 : 2))
+    return fail(CTR_ERR_INVALID_ARGUMENT, "num_vectors must be >= %d (got %d)", self ? 1 : 2, F);
   if (dim <= 0) return fail(CTR_ERR_INVALID_ARGUMENT, "dim must be positive");
   if (compute != CTR_F32 && compute != CTR_BF16)
     return fail(CTR_ERR_INVALID_ARGUMENT, "compute %d is not CTR_F32 or CTR_BF16", compute);
   if (batch > 0 && (!Z || !out)) return fail(CTR_ERR_INVALID_ARGUMENT, "Z and output are required");
-  const int64_t P = (int64_t)F * (F - 1) / 2;
+  const int64_t P = self ? (int64_t)F * (F + 1) / 2 : (int64_t)F * (F - 1) / 2;
   if (stride < dim + P) return fail(CTR_ERR_INVALID_ARGUMENT, "stride %lld < dim + P", (long long)stride);
   if (compute == CTR_BF16) {
-    if (!ctr::interaction_bf16_supported(F, dim))
+    if (!ctr::interaction_bf16_supported(F, dim, self))
       return fail(CTR_ERR_UNSUPPORTED, "bf16 path needs dim in {16,32,64,128}, F <= 128");
     if (Z && !aligned16(Z)) return fail(CTR_ERR_UNSUPPORTED, "Z is not 16-byte aligned");
-  } else if (!ctr::interaction_f32_supported(F, dim)) {
+  } else if (!ctr::interaction_f32_supported(F, dim, self)) {
     return fail(CTR_ERR_UNSUPPORTED, "fp32 path: one sample of F=%d, dim=%d exceeds 64 KiB of LDS", F, dim);
   }
   return CTR_OK;
 }
 
+static int32_t interaction_fwd_common(const float* Z, int64_t batch, int32_t F, int32_t dim,
+                                      int32_t compute, bool self, float* R, int64_t r_stride,
+                                      void* stream, const char* name) {
+  g_msg[0] = 0;
+  int32_t st = check_interaction(Z, batch, F, dim, compute, self, R, r_stride);
+  if (st) return st;
+  return hip_status(ctr::launch_interaction_fwd(Z, batch, F, dim, compute == CTR_BF16, self, R,
+                                                r_stride, (hipStream_t)stream),
+                    name);
+}
+
+static int32_t interaction_bwd_common(const float* Z, const float* dR, int64_t dr_stride,
+                                      int64_t batch, int32_t F, int32_t dim, int32_t compute,
+                                      bool self, float* dZ, void* stream, const char* name) {
+  g_msg[0] = 0;
+  int32_t st = check_interaction(Z, batch, F, dim, compute, self, dZ, dr_stride);
+  if (st) return st;
+  if (batch > 0 && !dR) return fail(CTR_ERR_INVALID_ARGUMENT, "dR is NULL");
+  return hip_status(ctr::launch_interaction_bwd(Z, dR, dr_stride, batch, F, dim,
+                                                compute == CTR_BF16, self, dZ,
+                                                (hipStream_t)stream),
+                    name);
+}
+
 int32_t ctr_dot_interaction_fwd(const float* Z, int64_t batch, int32_t num_vectors, int32_t dim,
                                 int32_t compute, float* R, int64_t r_stride, void* stream) {
-  g_msg[0] = 0;
-  int32_t st = check_interaction(Z, batch, num_vectors, dim, compute, R, r_stride);
-  if (st) return st;
-  return hip_status(ctr::launch_interaction_fwd(Z, batch, num_vectors, dim, compute == CTR_BF16,
-                                                R, r_stride, (hipStream_t)stream),
-                    "ctr_dot_interaction_fwd");
+  return interaction_fwd_common(Z, batch, num_vectors, dim, compute, false, R, r_stride, stream,
+                                "ctr_dot_interaction_fwd");
 }
 
 int32_t ctr_dot_interaction_bwd(const float* Z, const float* dR, int64_t dr_stride,
                                 int64_t batch, int32_t num_vectors, int32_t dim, int32_t compute,
                                 float* dZ, void* stream) {
+  return interaction_bwd_common(Z, dR, dr_stride, batch, num_vectors, dim, compute, false, dZ,
+                                stream, "ctr_dot_interaction_bwd");
+}
+
+int32_t ctr_dot_interaction_self_fwd(const float* Z, int64_t batch, int32_t num_vectors,
+                                     int32_t dim, int32_t compute, float* R, int64_t r_stride,
+                                     void* stream) {
+  return interaction_fwd_common(Z, batch, num_vectors, dim, compute, true, R, r_stride, stream,
+                                "ctr_dot_interaction_self_fwd");
+}
+
+int32_t ctr_dot_interaction_self_bwd(const float* Z, const float* dR, int64_t dr_stride,
+                                     int64_t batch, int32_t num_vectors, int32_t dim,
+                                     int32_t compute, float* dZ, void* stream) {
+  return interaction_bwd_common(Z, dR, dr_stride, batch, num_vectors, dim, compute, true, dZ,
+                                stream, "ctr_dot_interaction_self_bwd");
+}
+
+static int32_t check_fm(const float* Z, int64_t batch, int32_t F, int32_t dim, const float* a,
+                        const float* b) {
+  if (batch < 0 || batch > kMaxElems) return fail(CTR_ERR_INVALID_ARGUMENT, "bad batch");
+  if (F < 1) return fail(CTR_ERR_INVALID_ARGUMENT, "num_vectors must be >= 1 (got %d)", F);
+  if (dim <= 0) return fail(CTR_ERR_INVALID_ARGUMENT, "dim must be positive");
+  if ((int64_t)F * dim > kMaxElems) return fail(CTR_ERR_INVALID_ARGUMENT, "F * dim too large");
+  if (batch > 0 && (!Z || !a || !b))
+    return fail(CTR_ERR_INVALID_ARGUMENT, "Z and the other arrays are required");
+  return CTR_OK;
+}
+
+int32_t ctr_fm_interaction_fwd(const float* Z, int64_t batch, int32_t num_vectors, int32_t dim,
+                               float* out, void* stream) {
   g_msg[0] = 0;
-  int32_t st = check_interaction(Z, batch, num_vectors, dim, compute, dZ, dr_stride);
+  int32_t st = check_fm(Z, batch, num_vectors, dim, out, out);
   if (st) return st;
-  if (batch > 0 && !dR) return fail(CTR_ERR_INVALID_ARGUMENT, "dR is NULL");
-  return hip_status(ctr::launch_interaction_bwd(Z, dR, dr_stride, batch, num_vectors, dim,
-                                                compute == CTR_BF16, dZ, (hipStream_t)stream),
-                    "ctr_dot_interaction_bwd");
+  return hip_status(ctr::launch_fm_fwd(Z, batch, num_vectors, dim, out, (hipStream_t)stream),
+                    "ctr_fm_interaction_fwd");
+}
+
+int32_t ctr_fm_interaction_bwd(const float* Z, const float* dout, int64_t batch,
+                               int32_t num_vectors, int32_t dim, float* dZ, void* stream) {
+  g_msg[0] = 0;
+  int32_t st = check_fm(Z, batch, num_vectors, dim, dout, dZ);
+  if (st) return st;
+  return hip_status(ctr::launch_fm_bwd(Z, dout, batch, num_vectors, dim, dZ, (hipStream_t)stream),
+                    "ctr_fm_interaction_bwd");
 }
 
 int32_t ctr_init_table_hash(void* table, int32_t dtype, int32_t dim, const int64_t* row_base_host,

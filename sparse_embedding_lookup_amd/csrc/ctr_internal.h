@@ -149,12 +149,16 @@ hipError_t launch_embbag_bwd(const float* grad, int64_t sb, int64_t st, const in
                              uint64_t seed, void* workspace, hipStream_t s);
 
 // interaction.hip
-bool interaction_bf16_supported(int F, int dim);
-bool interaction_f32_supported(int F, int dim);
+bool interaction_bf16_supported(int F, int dim, bool self);
+bool interaction_f32_supported(int F, int dim, bool self);
 hipError_t launch_interaction_fwd(const float* Z, int64_t batch, int F, int dim, bool bf16,
-                                  float* R, int64_t r_stride, hipStream_t s);
+                                  bool self, float* R, int64_t r_stride, hipStream_t s);
 hipError_t launch_interaction_bwd(const float* Z, const float* dR, int64_t dr_stride,
-                                  int64_t batch, int F, int dim, bool bf16, float* dZ,
+                                  int64_t batch, int F, int dim, bool bf16, bool self, float* dZ,
                                   hipStream_t s);
+hipError_t launch_fm_fwd(const float* Z, int64_t batch, int F, int dim, float* out,
+                         hipStream_t s);
+hipError_t launch_fm_bwd(const float* Z, const float* dout, int64_t batch, int F, int dim,
+                         float* dZ, hipStream_t s);
 
 }  // namespace ctr

@@ -16,6 +16,14 @@
 //     Backward: dZ = S Z with S the symmetric zero-diagonal matrix of pair gradients
 //     (staged in LDS), A = S tiles, B = Z column slabs, fp32 accumulation.
 // Both paths are memory-bound on the 8 TB/s HBM: the arithmetic intensity is 6-14 flop/B.
+//
+// Variants ("DHEN" notes, 3.1 and Solution 2):
+//   SELF: the pairs i >= j, self-dots included ("all inner products for i <= j"):
+//     P = F(F+1)/2 in row-major lower-triangle order (index i(i+1)/2 + j), and the gradient
+//     of <z_i, z_i> is 2 z_i.  Every kernel below takes SELF as a template parameter.
+//   FM sum: per sample the sum of all pair dots by the squared-norm identity,
+//     out = 1/2 (||sum_i z_i||^2 - sum_i ||z_i||^2), O(F d) instead of O(F^2 d);
+//     dZ_i = dout * (sum_j z_j - z_i).
 #include "ctr_internal.h"
 
 namespace ctr {
@@ -39,6 +47,27 @@ __device__ __forceinline__ int tri_index(int i, int j) {
   return i > j ? i * (i - 1) / 2 + j : j * (j - 1) / 2 + i;
 }
 
+// Pair counts and indices of the two pair sets: strict (i > j) or with self-dots (i >= j).
+template <bool SELF>
+__host__ __device__ __forceinline__ int num_pairs(int F) {
+  return SELF ? F * (F + 1) / 2 : F * (F - 1) / 2;
+}
+template <bool SELF>
+__device__ __forceinline__ int pair_index(int i, int j) {     // requires i > j (i >= j: SELF)
+  return SELF ? i * (i + 1) / 2 + j : i * (i - 1) / 2 + j;
+}
+template <bool SELF>
+__device__ __forceinline__ int sym_pair_index(int i, int j) {
+  return i >= j ? pair_index<SELF>(i, j) : pair_index<SELF>(j, i);
+}
+// Row and column of pair index q.
+template <bool SELF>
+__device__ __forceinline__ void pair_of(int q, int* i, int* j) {
+  const int r = SELF ? tri_row(q) - 1 : tri_row(q);
+  *i = r;
+  *j = q - (SELF ? r * (r + 1) / 2 : r * (r - 1) / 2);
+}
+
 // An empty asm that claims to change an offset: loads addressed through it stay where they
 // are written instead of being hoisted out of a loop, which bounds register pressure.
 __device__ __forceinline__ int pinned_zero() {
@@ -55,6 +84,7 @@ __device__ __forceinline__ bf16x8 pack_bf16x8(const float* x) {
 }
 
 // ------------------------------------------------------------------------- fp32 forward
+template <bool SELF>
 __global__ __launch_bounds__(kThreads) void interaction_fwd_f32_kernel(
     const float* __restrict__ Z, int64_t batch, int F, int dim, int spb,
     float* __restrict__ R, int64_t r_stride) {
@@ -69,7 +99,7 @@ __global__ __launch_bounds__(kThreads) void interaction_fwd_f32_kernel(
     zs[(s * F + i) * ld + c] = Z[(b0 + s) * per + r];
   }
   __syncthreads();
-  const int P = F * (F - 1) / 2;
+  const int P = num_pairs<SELF>(F);
   const int W = dim + P;
   for (int q = threadIdx.x; q < nb * W; q += kThreads) {
     const int s = q / W, e = q - s * W;
@@ -77,9 +107,8 @@ __global__ __launch_bounds__(kThreads) void interaction_fwd_f32_kernel(
     if (e < dim) {
       v = zs[(s * F) * ld + e];
     } else {
-      const int pq = e - dim;
-      const int i = tri_row(pq);
-      const int j = pq - i * (i - 1) / 2;
+      int i, j;
+      pair_of<SELF>(e - dim, &i, &j);
       const float* zi = zs + (s * F + i) * ld;
       const float* zj = zs + (s * F + j) * ld;
       float acc = 0.f;
@@ -91,12 +120,13 @@ __global__ __launch_bounds__(kThreads) void interaction_fwd_f32_kernel(
 }
 
 // ------------------------------------------------------------------------- fp32 backward
+template <bool SELF>
 __global__ __launch_bounds__(kThreads) void interaction_bwd_f32_kernel(
     const float* __restrict__ Z, const float* __restrict__ dR, int64_t dr_stride,
     int64_t batch, int F, int dim, int spb, float* __restrict__ dZ) {
   extern __shared__ float smem[];
   const int ld = dim + 1;
-  const int P = F * (F - 1) / 2;
+  const int P = num_pairs<SELF>(F);
   float* zs = smem;                       // [spb][F][ld]
   float* ps = smem + spb * F * ld;        // [spb][P]
   const int64_t b0 = (int64_t)blockIdx.x * spb;
@@ -119,8 +149,11 @@ __global__ __launch_bounds__(kThreads) void interaction_bwd_f32_kernel(
     const float* zc = zs + (s * F) * ld + c;
     const float* pp = ps + s * P;
     for (int j = 0; j < F; ++j) {
-      if (j == i) continue;
-      acc = __builtin_fmaf(pp[tri_index(i, j)], zc[j * ld], acc);
+      if (j == i) {
+        if (SELF) acc = __builtin_fmaf(2.0f * pp[pair_index<true>(i, i)], zc[j * ld], acc);
+        continue;
+      }
+      acc = __builtin_fmaf(pp[sym_pair_index<SELF>(i, j)], zc[j * ld], acc);
     }
     dZ[(b0 + s) * per + r] = acc;
   }
@@ -137,13 +170,13 @@ constexpr int kLaneThreads = 64;
 // LDS (dynamic: samples x P x (L + 1) floats), and after one barrier lane l sums pairs
 // l, l + L, ... over the sample's L partials.  For FMAX = 32 (up to 496 pairs) the partials
 // are summed with xor shuffles instead.
-template <int FMAX, int L>
+template <int FMAX, int L, bool SELF>
 __global__ __launch_bounds__(kLaneThreads) void interaction_fwd_lanes_kernel(
     const float* __restrict__ Z, int64_t batch, int F, float* __restrict__ R, int64_t r_stride) {
   constexpr int kDim = 4 * L;
   constexpr bool kLds = FMAX <= 16;
   extern __shared__ float part[];              // [64 / L][P][L + 1] when kLds
-  const int P = F * (F - 1) / 2;
+  const int P = num_pairs<SELF>(F);
   const int lane = threadIdx.x % L;
   const int64_t b = (int64_t)blockIdx.x * (kLaneThreads / L) + threadIdx.x / L;
   const bool ok = b < batch;
@@ -163,9 +196,9 @@ __global__ __launch_bounds__(kLaneThreads) void interaction_fwd_lanes_kernel(
   float* ps = part + (int64_t)sl * P * (L + 1);
   int p = 0;
 #pragma unroll
-  for (int i = 1; i < FMAX; ++i) {
+  for (int i = SELF ? 0 : 1; i < FMAX; ++i) {
 #pragma unroll
-    for (int j = 0; j < i; ++j, ++p) {
+    for (int j = 0; j < (SELF ? i + 1 : i); ++j, ++p) {
       if (i < F) {
         float v = z[i].x * z[j].x;
         v = __builtin_fmaf(z[i].y, z[j].y, v);
@@ -195,15 +228,15 @@ __global__ __launch_bounds__(kLaneThreads) void interaction_fwd_lanes_kernel(
 
 // Backward: dZ_i = sum_{j != i} dP(i, j) z_j (+ dR_dense for i = 0), one output slice at a
 // time; the sample's pair gradients are staged in LDS and read as broadcasts.
-template <int FMAX, int L>
+template <int FMAX, int L, bool SELF>
 __global__ __launch_bounds__(kLaneThreads) void interaction_bwd_lanes_kernel(
     const float* __restrict__ Z, const float* __restrict__ dR, int64_t dr_stride, int64_t batch,
     int F, float* __restrict__ dZ) {
   constexpr int kDim = 4 * L;
   constexpr int kS = kLaneThreads / L;                     // samples per block
-  constexpr int kPmax = FMAX * (FMAX - 1) / 2;
+  constexpr int kPmax = SELF ? FMAX * (FMAX + 1) / 2 : FMAX * (FMAX - 1) / 2;
   __shared__ float dp[kS][kPmax];
-  const int P = F * (F - 1) / 2;
+  const int P = num_pairs<SELF>(F);
   const int64_t b0 = (int64_t)blockIdx.x * kS;
   for (int q = threadIdx.x; q < kS * P; q += kLaneThreads) {
     const int s = q / P, r = q - s * P;
@@ -227,8 +260,9 @@ __global__ __launch_bounds__(kLaneThreads) void interaction_bwd_lanes_kernel(
       float4 acc = i == 0 ? dense : make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
       for (int j = 0; j < FMAX; ++j) {
-        if (j != i && j < F) {
-          const float g = dp[sl][i > j ? i * (i - 1) / 2 + j : j * (j - 1) / 2 + i];
+        if ((SELF || j != i) && j < F) {
+          const float g = j == i ? 2.0f * dp[sl][pair_index<true>(i, i)]
+                                 : dp[sl][sym_pair_index<SELF>(i, j)];
           acc.x = __builtin_fmaf(g, z[j].x, acc.x);
           acc.y = __builtin_fmaf(g, z[j].y, acc.y);
           acc.z = __builtin_fmaf(g, z[j].z, acc.z);
@@ -259,9 +293,12 @@ __global__ __launch_bounds__(kLaneThreads) void interaction_bwd_lanes_kernel(
     else { CTR_LANES_L(32, __VA_ARGS__) }                                    \
   } while (0)
 
-bool lanes_shape(int F, int dim) {
+bool lanes_shape(int F, int dim, bool self) {
   const int L = dim / 4;
-  return F <= 32 && dim % 4 == 0 && L >= 1 && L <= 64 && (L & (L - 1)) == 0;
+  if (!(F <= 32 && dim % 4 == 0 && L >= 1 && L <= 64 && (L & (L - 1)) == 0)) return false;
+  // the forward's LDS partials (F <= 16) must fit one block's 64 KiB
+  const int P = self ? F * (F + 1) / 2 : F * (F - 1) / 2;
+  return F > 16 || (size_t)(kLaneThreads / L) * P * (L + 1) * sizeof(float) <= 65536;
 }
 
 // ------------------------------------------------------------------------- bf16 forward
@@ -290,7 +327,7 @@ __device__ __forceinline__ void load_row_block(const float* __restrict__ zb, int
 
 // FB: 32-row blocks covering F (F <= 32*FB); KS: dim / 16 (k-steps of 16).  Only two row
 // blocks of fragments are live at a time (the J block is re-read, from L1/L2).
-template <int FB, int KS>
+template <int FB, int KS, bool SELF>
 __global__ __launch_bounds__(kThreads) void interaction_fwd_mfma_kernel(
     const float* __restrict__ Z, int64_t batch, int F, float* __restrict__ R, int64_t r_stride) {
   constexpr int dim = KS * 16;
@@ -309,7 +346,7 @@ __global__ __launch_bounds__(kThreads) void interaction_fwd_mfma_kernel(
     load_row_block<KS>(zb, F, I, rl, kg, fa);
 #pragma unroll
     for (int J = 0; J <= I; ++J) {
-      if (J == I && F - 32 * I < 2) break;          // no pair i > j inside this tile
+      if (!SELF && J == I && F - 32 * I < 2) break;  // no pair i > j inside this tile
       bf16x8 fb[KS];
       if (J == I) {
 #pragma unroll
@@ -328,7 +365,7 @@ __global__ __launch_bounds__(kThreads) void interaction_fwd_mfma_kernel(
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int i = 32 * I + 8 * (v >> 2) + 4 * kg + (v & 3);
-        if (i < F && j < i) rb[dim + i * (i - 1) / 2 + j] = acc[v];
+        if (i < F && (SELF ? j <= i : j < i)) rb[dim + pair_index<SELF>(i, j)] = acc[v];
       }
     }
   }
@@ -338,7 +375,7 @@ __global__ __launch_bounds__(kThreads) void interaction_fwd_mfma_kernel(
 // One wave per sample; WPB samples per block; LDS holds each sample's pair gradients.
 // For each 32-row block of S (A operand, built once from LDS) and each 32-column slab of Z
 // (B operand, re-read per row block from L1/L2), 2*FB MFMAs give a 32x32 block of dZ.
-template <int FB, int KS>
+template <int FB, int KS, bool SELF>
 __global__ __launch_bounds__(kThreads) void interaction_bwd_mfma_kernel(
     const float* __restrict__ Z, const float* __restrict__ dR, int64_t dr_stride,
     int64_t batch, int F, int wpb, float* __restrict__ dZ) {
@@ -347,10 +384,10 @@ __global__ __launch_bounds__(kThreads) void interaction_bwd_mfma_kernel(
   extern __shared__ float sp_all[];
   const int lane = threadIdx.x & 63;
   const int wv = threadIdx.x >> 6;
-  const int P = F * (F - 1) / 2;
+  const int P = num_pairs<SELF>(F);
   const int64_t b = (int64_t)blockIdx.x * wpb + wv;
   const bool live = wv < wpb && b < batch;
-  float* sp = sp_all + wv * (P + 1);       // slot P holds 0: the diagonal and the padding
+  float* sp = sp_all + wv * (P + 1);       // slot P holds 0: the padding (and the diagonal)
   if (live) {
     for (int q = lane; q < P; q += 64) sp[q] = dR[b * dr_stride + dim + q];
     if (lane == 0) sp[P] = 0.f;
@@ -382,9 +419,10 @@ __global__ __launch_bounds__(kThreads) void interaction_bwd_mfma_kernel(
         const int j = 16 * s + 8 * kgx + e;
         const int vj = (int)((unsigned)(j - F) >> 31);           // 1 if j < F
         const int ne = (int)((0u - (unsigned)(i ^ j)) >> 31);    // 1 if i != j
-        const int ok = vi & vj & ne;
-        const int q = ok * tri_index(i, j) + (1 - ok) * P;
-        x[e] = sp[q];
+        const int ok = vi & vj & (SELF ? 1 : ne);
+        const int q = ok * (SELF ? sym_pair_index<true>(i, j) : tri_index(i, j)) + (1 - ok) * P;
+        // d<z_i, z_i>/dz_i = 2 z_i: the diagonal of S carries twice the self-dot gradient
+        x[e] = SELF ? sp[q] * (float)(2 - ne) : sp[q];
       }
       af[s] = pack_bf16x8(x);
     }
@@ -426,10 +464,84 @@ __global__ __launch_bounds__(kThreads) void interaction_bwd_mfma_kernel(
   }
 }
 
+// ------------------------------------------------------------------------- FM sum
+// One wave per sample, four per block.  Lane c (columns c, c + 64, ...) forms column c of
+// s = sum_i z_i and q = sum_i z_i^2 (loads coalesced across the lanes), and
+// out = 1/2 sum_c (s_c^2 - q_c) is summed over the wave with xor shuffles.
+__global__ __launch_bounds__(kThreads) void fm_fwd_kernel(const float* __restrict__ Z,
+                                                          int64_t batch, int F, int dim,
+                                                          float* __restrict__ out) {
+  const int lane = threadIdx.x & 63;
+  const int64_t b = (int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
+  if (b >= batch) return;
+  const float* zb = Z + b * (int64_t)F * dim;
+  float acc = 0.f;
+  for (int c = lane; c < dim; c += 64) {
+    float sc = 0.f, qc = 0.f;
+#pragma unroll 8
+    for (int i = 0; i < F; ++i) {
+      const float x = zb[(int64_t)i * dim + c];
+      sc += x;
+      qc = __builtin_fmaf(x, x, qc);
+    }
+    acc += __builtin_fmaf(sc, sc, -qc);
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) acc += __shfl_xor(acc, o, 64);
+  if (lane == 0) out[b] = 0.5f * acc;
+}
+
+// dZ[b, i, c] = dout[b] * (s_c - z_ic): the column sum first, then each row.  FMAX > 0:
+// the lane keeps its column of all F <= FMAX vectors in registers, so Z is read once;
+// FMAX = 0 (larger F): the rows are read again (from L2 when it still holds them).  The
+// column sum runs in the same order either way.
+template <int FMAX>
+__global__ __launch_bounds__(kThreads) void fm_bwd_kernel(const float* __restrict__ Z,
+                                                          const float* __restrict__ dout,
+                                                          int64_t batch, int F, int dim,
+                                                          float* __restrict__ dZ) {
+  const int lane = threadIdx.x & 63;
+  const int64_t b = (int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
+  if (b >= batch) return;
+  const float* zb = Z + b * (int64_t)F * dim;
+  float* db = dZ + b * (int64_t)F * dim;
+  const float g = dout[b];
+  for (int c = lane; c < dim; c += 64) {
+    float sc = 0.f;
+    if constexpr (FMAX > 0) {
+      // walking pointers with an opaque row stride: the row addresses are formed where they
+      // are used, not hoisted out of the column loop (which kept 2 x FMAX 64-bit addresses
+      // live)
+      const int ld = dim + pinned_zero();
+      float z[FMAX];
+      const float* zp = zb + c;
+#pragma unroll
+      for (int i = 0; i < FMAX; ++i) {
+        z[i] = i < F ? *zp : 0.f;
+        zp += ld;
+      }
+#pragma unroll
+      for (int i = 0; i < FMAX; ++i) sc += z[i];
+      const int ld2 = dim + pinned_zero();
+      float* dp = db + c;
+#pragma unroll
+      for (int i = 0; i < FMAX; ++i) {
+        if (i < F) *dp = g * (sc - z[i]);
+        dp += ld2;
+      }
+    } else {
+#pragma unroll 8
+      for (int i = 0; i < F; ++i) sc += zb[(int64_t)i * dim + c];
+#pragma unroll 8
+      for (int i = 0; i < F; ++i) db[(int64_t)i * dim + c] = g * (sc - zb[(int64_t)i * dim + c]);
+    }
+  }
+}
+
 // Samples per block of the fp32 kernels: as many as 32 KiB of LDS holds, but no more than
 // keeps about 1024 blocks in flight (four per CU), so small batches still fill the chip.
-int f32_spb(int64_t batch, int F, int dim, bool bwd) {
-  const int per = (F * (dim + 1) + (bwd ? F * (F - 1) / 2 : 0)) * 4;
+int f32_spb(int64_t batch, int F, int dim, bool bwd, bool self) {
+  const int per = (F * (dim + 1) + (bwd ? (self ? num_pairs<true>(F) : num_pairs<false>(F)) : 0)) * 4;
   int64_t spb = 32768 / per;
   const int64_t fill = batch / 1024;
   if (spb > fill) spb = fill;
@@ -440,17 +552,17 @@ int f32_spb(int64_t batch, int F, int dim, bool bwd) {
 
 }  // namespace
 
-bool interaction_bf16_supported(int F, int dim) {
+bool interaction_bf16_supported(int F, int dim, bool self) {
   if (dim % 16 != 0 || F > 128) return false;
   const int FB = (F + 31) / 32, KS = dim / 16;
   if (!(KS == 1 || KS == 2 || KS == 4 || KS == 8)) return false;
   if (FB * KS > 32) return false;                       // register budget of the forward
-  const int P = F * (F - 1) / 2;
+  const int P = self ? num_pairs<true>(F) : num_pairs<false>(F);
   return (P + 1) * 4 <= 65536;
 }
 
-bool interaction_f32_supported(int F, int dim) {
-  const int per = (F * (dim + 1) + F * (F - 1) / 2) * 4;
+bool interaction_f32_supported(int F, int dim, bool self) {
+  const int per = (F * (dim + 1) + (self ? num_pairs<true>(F) : num_pairs<false>(F))) * 4;
   return per <= 65536;
 }
 
@@ -462,57 +574,60 @@ bool interaction_f32_supported(int F, int dim) {
     default: { constexpr int FB = 4; __VA_ARGS__; } break; \
   }
 
-hipError_t launch_interaction_fwd(const float* Z, int64_t batch, int F, int dim, bool bf16,
-                                  float* R, int64_t r_stride, hipStream_t s) {
+namespace {
+
+template <bool SELF>
+hipError_t interaction_fwd(const float* Z, int64_t batch, int F, int dim, bool bf16, float* R,
+                           int64_t r_stride, hipStream_t s) {
   if (batch == 0) return hipSuccess;
+  const int P = num_pairs<SELF>(F);
   if (!bf16) {
-    if (lanes_shape(F, dim)) {
+    if (lanes_shape(F, dim, SELF)) {
       const int L_ = dim / 4;
       const int64_t blocks = (batch * L_ + kLaneThreads - 1) / kLaneThreads;
-      const size_t lds = F <= 16 ? (size_t)(kLaneThreads / L_) * (F * (F - 1) / 2) * (L_ + 1) *
-                                       sizeof(float) : 0;
-      CTR_LANES(F, L_, interaction_fwd_lanes_kernel<FMAX, L><<<(unsigned)blocks, kLaneThreads, lds, s>>>(
+      const size_t lds = F <= 16 ? (size_t)(kLaneThreads / L_) * P * (L_ + 1) * sizeof(float) : 0;
+      CTR_LANES(F, L_, interaction_fwd_lanes_kernel<FMAX, L, SELF><<<(unsigned)blocks, kLaneThreads, lds, s>>>(
                            Z, batch, F, R, r_stride));
       return hipGetLastError();
     }
-    const int spb = f32_spb(batch, F, dim, false);
+    const int spb = f32_spb(batch, F, dim, false, SELF);
     const size_t lds = (size_t)spb * F * (dim + 1) * sizeof(float);
     const int64_t blocks = (batch + spb - 1) / spb;
-    interaction_fwd_f32_kernel<<<(unsigned)blocks, kThreads, lds, s>>>(Z, batch, F, dim, spb, R,
-                                                                       r_stride);
+    interaction_fwd_f32_kernel<SELF><<<(unsigned)blocks, kThreads, lds, s>>>(Z, batch, F, dim, spb,
+                                                                             R, r_stride);
     return hipGetLastError();
   }
   const int FB = (F + 31) / 32, KS = dim / 16;
   const int64_t blocks = (batch + 3) / 4;
   CTR_FB_DISPATCH(FB, {
     switch (KS) {
-      case 1: interaction_fwd_mfma_kernel<FB, 1><<<(unsigned)blocks, kThreads, 0, s>>>(Z, batch, F, R, r_stride); break;
-      case 2: interaction_fwd_mfma_kernel<FB, 2><<<(unsigned)blocks, kThreads, 0, s>>>(Z, batch, F, R, r_stride); break;
-      case 4: interaction_fwd_mfma_kernel<FB, 4><<<(unsigned)blocks, kThreads, 0, s>>>(Z, batch, F, R, r_stride); break;
-      default: interaction_fwd_mfma_kernel<FB, 8><<<(unsigned)blocks, kThreads, 0, s>>>(Z, batch, F, R, r_stride); break;
+      case 1: interaction_fwd_mfma_kernel<FB, 1, SELF><<<(unsigned)blocks, kThreads, 0, s>>>(Z, batch, F, R, r_stride); break;
+      case 2: interaction_fwd_mfma_kernel<FB, 2, SELF><<<(unsigned)blocks, kThreads, 0, s>>>(Z, batch, F, R, r_stride); break;
+      case 4: interaction_fwd_mfma_kernel<FB, 4, SELF><<<(unsigned)blocks, kThreads, 0, s>>>(Z, batch, F, R, r_stride); break;
+      default: interaction_fwd_mfma_kernel<FB, 8, SELF><<<(unsigned)blocks, kThreads, 0, s>>>(Z, batch, F, R, r_stride); break;
     }
   });
   return hipGetLastError();
 }
 
-hipError_t launch_interaction_bwd(const float* Z, const float* dR, int64_t dr_stride,
-                                  int64_t batch, int F, int dim, bool bf16, float* dZ,
-                                  hipStream_t s) {
+template <bool SELF>
+hipError_t interaction_bwd(const float* Z, const float* dR, int64_t dr_stride, int64_t batch,
+                           int F, int dim, bool bf16, float* dZ, hipStream_t s) {
   if (batch == 0) return hipSuccess;
-  const int P = F * (F - 1) / 2;
+  const int P = num_pairs<SELF>(F);
   if (!bf16) {
-    if (lanes_shape(F, dim)) {
+    if (lanes_shape(F, dim, SELF)) {
       const int L_ = dim / 4;
       const int64_t blocks = (batch * L_ + kLaneThreads - 1) / kLaneThreads;
-      CTR_LANES(F, L_, interaction_bwd_lanes_kernel<FMAX, L><<<(unsigned)blocks, kLaneThreads, 0, s>>>(
+      CTR_LANES(F, L_, interaction_bwd_lanes_kernel<FMAX, L, SELF><<<(unsigned)blocks, kLaneThreads, 0, s>>>(
                            Z, dR, dr_stride, batch, F, dZ));
       return hipGetLastError();
     }
-    const int spb = f32_spb(batch, F, dim, true);
+    const int spb = f32_spb(batch, F, dim, true, SELF);
     const size_t lds = (size_t)spb * (F * (dim + 1) + P) * sizeof(float);
     const int64_t blocks = (batch + spb - 1) / spb;
-    interaction_bwd_f32_kernel<<<(unsigned)blocks, kThreads, lds, s>>>(Z, dR, dr_stride, batch,
-                                                                       F, dim, spb, dZ);
+    interaction_bwd_f32_kernel<SELF><<<(unsigned)blocks, kThreads, lds, s>>>(Z, dR, dr_stride,
+                                                                             batch, F, dim, spb, dZ);
     return hipGetLastError();
   }
   const int FB = (F + 31) / 32;
@@ -524,12 +639,51 @@ hipError_t launch_interaction_bwd(const float* Z, const float* dR, int64_t dr_st
   const int KS = dim / 16;
   CTR_FB_DISPATCH(FB, {
     switch (KS) {
-      case 1: interaction_bwd_mfma_kernel<FB, 1><<<(unsigned)blocks, kThreads, lds, s>>>(Z, dR, dr_stride, batch, F, wpb, dZ); break;
-      case 2: interaction_bwd_mfma_kernel<FB, 2><<<(unsigned)blocks, kThreads, lds, s>>>(Z, dR, dr_stride, batch, F, wpb, dZ); break;
-      case 4: interaction_bwd_mfma_kernel<FB, 4><<<(unsigned)blocks, kThreads, lds, s>>>(Z, dR, dr_stride, batch, F, wpb, dZ); break;
-      default: interaction_bwd_mfma_kernel<FB, 8><<<(unsigned)blocks, kThreads, lds, s>>>(Z, dR, dr_stride, batch, F, wpb, dZ); break;
+      case 1: interaction_bwd_mfma_kernel<FB, 1, SELF><<<(unsigned)blocks, kThreads, lds, s>>>(Z, dR, dr_stride, batch, F, wpb, dZ); break;
+      case 2: interaction_bwd_mfma_kernel<FB, 2, SELF><<<(unsigned)blocks, kThreads, lds, s>>>(Z, dR, dr_stride, batch, F, wpb, dZ); break;
+      case 4: interaction_bwd_mfma_kernel<FB, 4, SELF><<<(unsigned)blocks, kThreads, lds, s>>>(Z, dR, dr_stride, batch, F, wpb, dZ); break;
+      default: interaction_bwd_mfma_kernel<FB, 8, SELF><<<(unsigned)blocks, kThreads, lds, s>>>(Z, dR, dr_stride, batch, F, wpb, dZ); break;
     }
   });
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_interaction_fwd(const float* Z, int64_t batch, int F, int dim, bool bf16,
+                                  bool self, float* R, int64_t r_stride, hipStream_t s) {
+  return self ? interaction_fwd<true>(Z, batch, F, dim, bf16, R, r_stride, s)
+              : interaction_fwd<false>(Z, batch, F, dim, bf16, R, r_stride, s);
+}
+
+hipError_t launch_interaction_bwd(const float* Z, const float* dR, int64_t dr_stride,
+                                  int64_t batch, int F, int dim, bool bf16, bool self, float* dZ,
+                                  hipStream_t s) {
+  return self ? interaction_bwd<true>(Z, dR, dr_stride, batch, F, dim, bf16, dZ, s)
+              : interaction_bwd<false>(Z, dR, dr_stride, batch, F, dim, bf16, dZ, s);
+}
+
+hipError_t launch_fm_fwd(const float* Z, int64_t batch, int F, int dim, float* out,
+                         hipStream_t s) {
+  if (batch == 0) return hipSuccess;
+  const int64_t blocks = (batch + 3) / 4;
+  fm_fwd_kernel<<<(unsigned)blocks, kThreads, 0, s>>>(Z, batch, F, dim, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_fm_bwd(const float* Z, const float* dout, int64_t batch, int F, int dim,
+                         float* dZ, hipStream_t s) {
+  if (batch == 0) return hipSuccess;
+  const int64_t blocks = (batch + 3) / 4;
+#define CTR_FM_BWD(FM) \
+  fm_bwd_kernel<FM><<<(unsigned)blocks, kThreads, 0, s>>>(Z, dout, batch, F, dim, dZ)
+  if (F <= 16) CTR_FM_BWD(16);
+  else if (F <= 32) CTR_FM_BWD(32);
+  else if (F <= 64) CTR_FM_BWD(64);
+  else if (F <= 96) CTR_FM_BWD(96);
+  else if (F <= 128) CTR_FM_BWD(128);
+  else CTR_FM_BWD(0);
+#undef CTR_FM_BWD
   return hipGetLastError();
 }
 

@@ -25,6 +25,8 @@ EXPORTED = [
     "ctr_dot_interaction_fwd",
     "ctr_dot_interaction_bwd", "ctr_init_table_hash", "ctr_validate_csr", "ctr_step_run",
     "ctr_step_unique", "ctr_embbag_bwd_sgd_sr", "ctr_sparse_sgd_sr", "ctr_sr_step_seed",
+    "ctr_dot_interaction_self_fwd", "ctr_dot_interaction_self_bwd", "ctr_fm_interaction_fwd",
+    "ctr_fm_interaction_bwd",
 ]
 
 CTR_STEP_POOLED_INTERACTION, CTR_STEP_BATCH_MATRIX = 0, 1
@@ -89,6 +91,10 @@ def load() -> ctypes.CDLL:
                                         P, f32, u64, P, P, PS, P]),
         "ctr_sparse_sgd_sr": (i32, [P, i32, i64, i32, P, P, i64, P, f32, u64, P]),
         "ctr_sr_step_seed": (u64, [u64, i64]),
+        "ctr_dot_interaction_self_fwd": (i32, [P, i64, i32, i32, i32, P, i64, P]),
+        "ctr_dot_interaction_self_bwd": (i32, [P, P, i64, i64, i32, i32, i32, P, P]),
+        "ctr_fm_interaction_fwd": (i32, [P, i64, i32, i32, P, P]),
+        "ctr_fm_interaction_bwd": (i32, [P, P, i64, i32, i32, P, P]),
         "ctr_dot_interaction_fwd": (i32, [P, i64, i32, i32, i32, P, i64, P]),
         "ctr_dot_interaction_bwd": (i32, [P, P, i64, i64, i32, i32, i32, P, P]),
         "ctr_init_table_hash": (i32, [P, i32, i32, P, i32, u64, P]),
@@ -344,6 +350,48 @@ def ctr_dot_interaction_bwd(Z: torch.Tensor, dR: torch.Tensor, compute: int = CT
         dZ = torch.empty_like(Z)
     args = (_ptr(Z), _ptr(dR), dR.stride(0), B, F, d, compute, _ptr(dZ))
     return _run("ctr_dot_interaction_bwd", args, stream, prepare, dZ)
+
+
+def ctr_dot_interaction_self_fwd(Z: torch.Tensor, compute: int = CTR_F32,
+                                 R: Optional[torch.Tensor] = None, stream=None,
+                                 prepare: bool = False):
+    """Pair dots with self-dots (i >= j), P = F(F+1)/2: R = [dense | pairs]."""
+    B, F, d = Z.shape
+    P = F * (F + 1) // 2
+    if R is None:
+        R = torch.empty((B, d + P), dtype=torch.float32, device=Z.device)
+    args = (_ptr(Z), B, F, d, compute, _ptr(R), R.stride(0))
+    return _run("ctr_dot_interaction_self_fwd", args, stream, prepare, R)
+
+
+def ctr_dot_interaction_self_bwd(Z: torch.Tensor, dR: torch.Tensor, compute: int = CTR_F32,
+                                 dZ: Optional[torch.Tensor] = None, stream=None,
+                                 prepare: bool = False):
+    B, F, d = Z.shape
+    if dZ is None:
+        dZ = torch.empty_like(Z)
+    args = (_ptr(Z), _ptr(dR), dR.stride(0), B, F, d, compute, _ptr(dZ))
+    return _run("ctr_dot_interaction_self_bwd", args, stream, prepare, dZ)
+
+
+def ctr_fm_interaction_fwd(Z: torch.Tensor, out: Optional[torch.Tensor] = None, stream=None,
+                           prepare: bool = False):
+    """Sum of all pair dots per sample by the squared-norm identity: out [B]."""
+    B, F, d = Z.shape
+    if out is None:
+        out = torch.empty((B,), dtype=torch.float32, device=Z.device)
+    args = (_ptr(Z), B, F, d, _ptr(out))
+    return _run("ctr_fm_interaction_fwd", args, stream, prepare, out)
+
+
+def ctr_fm_interaction_bwd(Z: torch.Tensor, dout: torch.Tensor,
+                           dZ: Optional[torch.Tensor] = None, stream=None,
+                           prepare: bool = False):
+    B, F, d = Z.shape
+    if dZ is None:
+        dZ = torch.empty_like(Z)
+    args = (_ptr(Z), _ptr(dout), B, F, d, _ptr(dZ))
+    return _run("ctr_fm_interaction_bwd", args, stream, prepare, dZ)
 
 
 def ctr_init_table_hash(table: torch.Tensor, rows: Sequence[int], seed: int, stream=None) -> None:

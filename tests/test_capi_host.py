@@ -174,6 +174,23 @@ def test_stochastic_rounding_entry_points_bad_args():
     assert wsb.value > 0                          # the workspace query of ctr_embbag_bwd
 
 
+def test_interaction_variant_bad_args():
+    lib = _lib()
+    f = lib.ctr_dot_interaction_self_fwd
+    # F = 5, dim = 16: the self-dot set needs dim + 15 columns, the strict one dim + 10
+    assert f(FAKE, 10, 5, 16, ctr.CTR_F32, FAKE, 16 + 10, None) == ctr.CTR_ERR_INVALID_ARGUMENT
+    assert b"stride" in lib.ctr_last_error()
+    assert f(FAKE, 10, 0, 16, ctr.CTR_F32, FAKE, 100, None) == ctr.CTR_ERR_INVALID_ARGUMENT
+    assert f(FAKE, 10, 5, 24, ctr.CTR_BF16, FAKE, 100, None) == ctr.CTR_ERR_UNSUPPORTED
+    b = lib.ctr_dot_interaction_self_bwd
+    assert b(FAKE, None, 31, 10, 5, 16, ctr.CTR_F32, FAKE, None) == ctr.CTR_ERR_INVALID_ARGUMENT
+    assert lib.ctr_fm_interaction_fwd(FAKE, 10, 0, 16, FAKE, None) == \
+        ctr.CTR_ERR_INVALID_ARGUMENT
+    assert lib.ctr_fm_interaction_bwd(FAKE, None, 10, 3, 16, FAKE, None) == \
+        ctr.CTR_ERR_INVALID_ARGUMENT
+    assert lib.ctr_fm_interaction_fwd(None, 0, 3, 16, None, None) == ctr.CTR_OK   # empty batch
+
+
 def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
     monkeypatch.setattr(ctr, "LIB_PATH", str(tmp_path / "missing.so"))
     monkeypatch.setattr(ctr, "_lib", None)
