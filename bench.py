@@ -105,6 +105,49 @@ SINGLE_KERNEL = {
 }
 
 
+class TimingEvent:
+    """A HIP timing event created with hipEventDisableSystemFence: HIP documents the flag for
+    events that only measure time.  Recording skips the system-scope release, which is a
+    cache writeback and invalidation, so the bracket around one kernel is closer to the
+    kernel itself.  On the Small workload's pooling kernel this reads 17.0-17.4 us, against
+    18.7-19.8 us for a default event, with rocprofv3 at 14.1-15.1 us.  It takes the HIP
+    runtime already loaded in the process (the one torch and libctr share), and exposes
+    .cuda_event like torch.cuda.Event so that ctr_step_run takes it as a mark."""
+    _hip = None
+    DISABLE_SYSTEM_FENCE = 0x20000000
+
+    def __init__(self):
+        import ctypes
+        if TimingEvent._hip is None:
+            path = [ln.split()[-1] for ln in open("/proc/self/maps") if "libamdhip64" in ln][0]
+            TimingEvent._hip = ctypes.CDLL(path)
+        h = ctypes.c_void_p()
+        st = TimingEvent._hip.hipEventCreateWithFlags(ctypes.byref(h),
+                                                      ctypes.c_uint(self.DISABLE_SYSTEM_FENCE))
+        if st != 0:
+            raise RuntimeError("hipEventCreateWithFlags failed (%d)" % st)
+        self.cuda_event = h.value
+
+    def record(self, stream=None):
+        import ctypes
+        import torch
+        s = stream if stream is not None else torch.cuda.current_stream()
+        st = TimingEvent._hip.hipEventRecord(ctypes.c_void_p(self.cuda_event),
+                                             ctypes.c_void_p(s.cuda_stream))
+        if st != 0:
+            raise RuntimeError("hipEventRecord failed (%d)" % st)
+
+    def elapsed_time(self, end) -> float:
+        import ctypes
+        ms = ctypes.c_float()
+        st = TimingEvent._hip.hipEventElapsedTime(ctypes.byref(ms),
+                                                  ctypes.c_void_p(self.cuda_event),
+                                                  ctypes.c_void_p(end.cuda_event))
+        if st != 0:
+            raise RuntimeError("hipEventElapsedTime failed (%d)" % st)
+        return ms.value
+
+
 def time_variants(fe, w, K: int):
     """The interaction variants on the workload's Z (after the timed steps), each call alone
     bracketed by HIP events: the pair set with self-dots, forward and backward (P = F(F+1)/2),
@@ -402,10 +445,8 @@ def main():
     # event-record nodes of the captured steps, so the replay leaves them timed).
     print("[bench] timing %d steps (%s, %s)" % (K, args.launch, "pipelined" if pipelined
                                                 else "serial"), file=sys.stderr, flush=True)
-    dev0 = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
-    dev1 = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
-    for e in dev0 + dev1:
-        e.record()                       # torch creates the HIP event on its first record
+    dev0 = [TimingEvent() for _ in range(K)]
+    dev1 = [TimingEvent() for _ in range(K)]
     torch.cuda.synchronize()
     if graph:
         g_steps = fe.capture_native(K, sched, [e for pair in zip(dev0, dev1) for e in pair])
