@@ -278,6 +278,48 @@ int32_t ctr_init_table_hash(void* table, int32_t dtype, int32_t dim,
                             void* stream);
 
 /*
+ * ---------------------------------------------------------------- exported dictionary
+ * Inference-side lookup by raw 64-bit ID ([TN] "Inference Optimization": online inference
+ * reads a pre-exported sparse embedding dictionary; no modulus), with a hot-row cache in HBM
+ * in front of the full table ("Tera-scale training" review, hardware-aware framework figure:
+ * GPU HBM holds the hot parameters of a hierarchical parameter server, CPU memory the warm
+ * ones).
+ *
+ * ctr_dict_build -- the dictionary's hash table.  Key keys[i] (>= 0, distinct) maps to
+ * dictionary-table row rows[i] and, when hot_slots is not NULL and hot_slots[i] >= 0, to
+ * row hot_slots[i] of the HBM cache.  slots: device memory of capacity * 16 bytes (16-byte
+ * aligned), capacity a power of two > n; the call clears it first.  Open addressing: the
+ * home slot is splitmix64(key) mod capacity, linear probing.  status: int32[3] on the
+ * device, set to the number of repeated keys (the value kept is one of theirs), negative
+ * keys (skipped) and keys left without a slot (0 when n < capacity).
+ */
+int32_t ctr_dict_build(const int64_t* keys, const int32_t* rows, const int32_t* hot_slots,
+                       int64_t n, void* slots, int64_t capacity, int32_t* status, void* stream);
+
+/*
+ * ctr_dict_lookup -- values[i] for ids[i]: the slot value ((cache slot + 1) << 32 | row,
+ * cache slot + 1 = 0 when not cached), or -1 when ids[i] is not in the dictionary.
+ * ids, values: int64 [n] device.
+ */
+int32_t ctr_dict_lookup(const int64_t* ids, int64_t n, const void* slots, int64_t capacity,
+                        int64_t* values, void* stream);
+
+/*
+ * ctr_dict_embbag_fwd -- sum pooling over looked-up values (bags as in ctr_embbag_fwd):
+ *   out[b*out_stride_b + t*out_stride_t + c] = sum over the bag's occurrences k of
+ *     hot_rows[slot][c]   when values[k] carries cache slot `slot` < num_hot,
+ *     table[row][c]       otherwise, row = low 32 bits of values[k] (< num_rows),
+ *   where values[k] = -1 (not in the dictionary) adds nothing.  table: [num_rows, dim] of
+ * dtype, the whole dictionary; it may be pinned host memory (hipHostMalloc, device-mapped),
+ * read over the host link.  hot_rows: [num_hot, dim] of dtype in HBM, or NULL.
+ */
+int32_t ctr_dict_embbag_fwd(const int64_t* values, int64_t nnz, const int64_t* offsets,
+                            int64_t batch, int32_t num_tables, const void* hot_rows,
+                            int64_t num_hot, const void* table, int64_t num_rows, int32_t dtype,
+                            int32_t dim, float* out, int64_t out_stride_b,
+                            int64_t out_stride_t, void* stream);
+
+/*
  * ctr_validate_csr -- debug check of the data preconditions: offsets[0] == 0, offsets
  * non-decreasing, offsets[last] == nnz, and 0 <= indices[k] < rows of the bag's table
  * (row_base given: rows_t = row_base[t+1] - row_base[t]; else total_rows).  Adds the number

@@ -26,6 +26,8 @@
  *           between all pairs of embedding vectors and the processed dense features.
  *           Section 3.1 also names the pair set i <= j with self-dots; Solution 2 the FM
  *           sum of all pair dots by the squared-norm identity.
+ *           [TN] "Inference Optimization": online inference reads a pre-exported sparse
+ *           embedding dictionary keyed by raw ID.
  *           Section 6.4 "Common Optimizations": low-precision (FP16) embedding storage
  *           whose updates use stochastic rounding.
  * Readings where the pages are silent (sum pooling, strict i > j pair order, sum of
@@ -453,6 +455,64 @@ void orc_fm_bwd(const double* Z, const double* zmag, const double* dout, int64_t
         dZ[(b * F + i) * dim + c] = dout[b] * s;
         dmag[(b * F + i) * dim + c] = fabs(dout[b]) * a;
       }
+  }
+}
+
+/* ------------------------------------------------------------------ exported dictionary */
+/* [TN] "Inference Optimization": online inference looks raw IDs up in a pre-exported sparse
+ * embedding dictionary.  The dictionary is the list (keys[e], rows[e], hot[e]) of its n
+ * entries; the value of ID x is ((hot[e] + 1) << 32) | rows[e] for the entry with
+ * keys[e] == x, or -1 when there is none (negative IDs have none).  Written as a search
+ * over the entries sorted by key (`order`, a permutation the caller gets from a library
+ * sort), one binary search per ID. */
+void orc_dict_lookup(const int64_t* keys, const int32_t* rows, const int32_t* hot,
+                     const int64_t* order, int64_t n, const int64_t* ids, int64_t m,
+                     int64_t* values) {
+#pragma omp parallel for schedule(static)
+  for (int64_t i = 0; i < m; ++i) {
+    int64_t x = ids[i], lo = 0, hi = n, v = -1;
+    while (lo < hi) {                              /* first sorted entry with key >= x */
+      int64_t mid = lo + (hi - lo) / 2;
+      if (keys[order[mid]] < x) lo = mid + 1; else hi = mid;
+    }
+    if (x >= 0 && lo < n && keys[order[lo]] == x) {
+      int64_t e = order[lo];
+      uint64_t hs = hot ? (uint64_t)(uint32_t)(hot[e] + 1) : 0u;
+      v = (int64_t)((hs << 32) | (uint32_t)rows[e]);
+    }
+    values[i] = v;
+  }
+}
+
+/* Sum pooling over looked-up values: out[b][t][c] = sum over the bag's occurrences with
+ * values[k] >= 0 of W[row][c], row = the low 32 bits of values[k] (the cache holds copies
+ * of dictionary rows, so the cached or the table copy is the same value).  W is the
+ * dictionary table (one table of num_rows rows, the counter-based fill or `data`). */
+void orc_dict_pool(const float* data, uint64_t seed, int64_t num_rows, int32_t dim,
+                   int32_t bf16, const int64_t* values, const int64_t* offsets, int64_t batch,
+                   int32_t num_tables, double* out, double* omag) {
+  int64_t rb[2] = {0, num_rows};
+  orc_table tb = {data, seed, rb, 1, dim, bf16};
+  int64_t nb = (int64_t)num_tables * batch;
+#pragma omp parallel for schedule(static)
+  for (int64_t s = 0; s < nb; ++s) {
+    int64_t t = s / batch, b = s - t * batch;
+    double* o = out + (b * num_tables + t) * dim;
+    double* om = omag + (b * num_tables + t) * dim;
+    for (int64_t c = 0; c < dim; ++c) {
+      o[c] = 0.0;
+      om[c] = 0.0;
+    }
+    for (int64_t k = offsets[s]; k < offsets[s + 1]; ++k) {
+      if (values[k] < 0) continue;
+      int64_t row = (int64_t)(uint32_t)values[k];
+      if (row >= num_rows) continue;
+      for (int64_t c = 0; c < dim; ++c) {
+        double w = tval(&tb, row, c);
+        o[c] += w;
+        om[c] += fabs(w);
+      }
+    }
   }
 }
 

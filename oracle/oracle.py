@@ -61,6 +61,8 @@ def _load():
         "orc_interaction_self_bwd": (None, [P, P, P, i64, i32, i32, P, P]),
         "orc_fm_fwd": (None, [P, P, i64, i32, i32, P, P]),
         "orc_fm_bwd": (None, [P, P, P, i64, i32, i32, P, P]),
+        "orc_dict_lookup": (None, [P, P, P, P, i64, P, i64, P]),
+        "orc_dict_pool": (None, [P, u64, i64, i32, i32, P, P, i64, i32, P, P]),
         "orc_sr_bf16": (f64, [f64, ctypes.c_uint32]),
         "orc_sr_bits": (ctypes.c_uint32, [u64, i64, i64, i32]),
         "orc_sparse_sgd_sr": (None, [P, u64, P, i32, i32, P, i64, P, f32, u64, P]),
@@ -303,3 +305,29 @@ def sparse_sgd_sr(tab: Table, uniq, g, lr: float, sr_seed: int):
     _load().orc_sparse_sgd_sr(*tab.args()[:5], _p(uniq), U, _p(g), ctypes.c_float(lr),
                               ctypes.c_uint64(sr_seed & 0xFFFFFFFFFFFFFFFF), _p(out))
     return out
+
+
+def dict_lookup(keys, rows, hot, ids):
+    """Values of `ids` in the dictionary (keys, rows, hot): ((hot+1) << 32) | row, or -1."""
+    keys = _c(keys, np.int64)
+    rows = _c(rows, np.int32)
+    hot = None if hot is None else _c(hot, np.int32)
+    order = _c(np.argsort(keys, kind="stable"), np.int64)
+    ids = _c(ids, np.int64)
+    out = np.empty(ids.size, dtype=np.int64)
+    _load().orc_dict_lookup(_p(keys), _p(rows), _p(hot), _p(order), keys.size, _p(ids), ids.size,
+                            _p(out))
+    return out
+
+
+def dict_pool(tab: "Table", values, offsets, batch: int, num_tables: int):
+    """Sum pooling over looked-up values, from the dictionary table `tab` (one table):
+    returns (out, mag) [batch, num_tables, dim] float64."""
+    assert tab.num_tables == 1
+    values = _c(values, np.int64)
+    offsets = _c(offsets, np.int64)
+    out = np.empty((batch, num_tables, tab.dim), dtype=np.float64)
+    om = np.empty_like(out)
+    _load().orc_dict_pool(_p(tab.data), tab.seed, tab.total_rows, tab.dim, tab.bf16, _p(values),
+                          _p(offsets), batch, num_tables, _p(out), _p(om))
+    return out, om

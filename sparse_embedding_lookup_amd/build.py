@@ -14,7 +14,8 @@ CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libctr.so")
 OBJ = os.path.join(HERE, "_build")
 
-SOURCES = ["capi.cpp", "step.cpp", "unique.hip", "embbag.hip", "segreduce.hip", "interaction.hip"]
+SOURCES = ["capi.cpp", "step.cpp", "unique.hip", "embbag.hip", "segreduce.hip", "interaction.hip",
+           "dict.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

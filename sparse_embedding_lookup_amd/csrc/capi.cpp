@@ -431,6 +431,69 @@ int32_t ctr_fm_interaction_bwd(const float* Z, const float* dout, int64_t batch,
                     "ctr_fm_interaction_bwd");
 }
 
+static bool pow2(int64_t x) { return x > 0 && (x & (x - 1)) == 0; }
+
+int32_t ctr_dict_build(const int64_t* keys, const int32_t* rows, const int32_t* hot_slots,
+                       int64_t n, void* slots, int64_t capacity, int32_t* status,
+                       void* stream) {
+  g_msg[0] = 0;
+  if (n < 0 || n > kMaxElems) return fail(CTR_ERR_INVALID_ARGUMENT, "bad n");
+  if (!pow2(capacity) || capacity < 2)
+    return fail(CTR_ERR_INVALID_ARGUMENT, "capacity %lld is not a power of two >= 2",
+                (long long)capacity);
+  if (n >= capacity)
+    return fail(CTR_ERR_INVALID_ARGUMENT, "n = %lld keys need capacity > n (got %lld)",
+                (long long)n, (long long)capacity);
+  if (!slots || !status) return fail(CTR_ERR_INVALID_ARGUMENT, "slots and status are required");
+  if (n > 0 && (!keys || !rows)) return fail(CTR_ERR_INVALID_ARGUMENT, "keys and rows are required");
+  if (!aligned16(slots)) return fail(CTR_ERR_UNSUPPORTED, "slots is not 16-byte aligned");
+  return hip_status(ctr::launch_dict_build(keys, rows, hot_slots, n, slots, capacity, status,
+                                           (hipStream_t)stream),
+                    "ctr_dict_build");
+}
+
+int32_t ctr_dict_lookup(const int64_t* ids, int64_t n, const void* slots, int64_t capacity,
+                        int64_t* values, void* stream) {
+  g_msg[0] = 0;
+  if (n < 0 || n > kMaxElems) return fail(CTR_ERR_INVALID_ARGUMENT, "bad n");
+  if (!pow2(capacity) || capacity < 2)
+    return fail(CTR_ERR_INVALID_ARGUMENT, "capacity %lld is not a power of two >= 2",
+                (long long)capacity);
+  if (n > 0 && (!ids || !slots || !values))
+    return fail(CTR_ERR_INVALID_ARGUMENT, "ids, slots and values are required");
+  if (slots && !aligned16(slots)) return fail(CTR_ERR_UNSUPPORTED, "slots is not 16-byte aligned");
+  return hip_status(ctr::launch_dict_lookup(ids, n, slots, capacity, values, (hipStream_t)stream),
+                    "ctr_dict_lookup");
+}
+
+int32_t ctr_dict_embbag_fwd(const int64_t* values, int64_t nnz, const int64_t* offsets,
+                            int64_t batch, int32_t num_tables, const void* hot_rows,
+                            int64_t num_hot, const void* table, int64_t num_rows, int32_t dtype,
+                            int32_t dim, float* out, int64_t out_stride_b,
+                            int64_t out_stride_t, void* stream) {
+  g_msg[0] = 0;
+  int32_t st = check_table(table, dtype, num_rows, dim);
+  if (st) return st;
+  if (num_rows < 1) return fail(CTR_ERR_INVALID_ARGUMENT, "the dictionary table needs >= 1 row");
+  if (num_hot < 0) return fail(CTR_ERR_INVALID_ARGUMENT, "num_hot < 0");
+  if (num_hot > 0 && !hot_rows) return fail(CTR_ERR_INVALID_ARGUMENT, "hot_rows is NULL");
+  if (hot_rows && !aligned16(hot_rows))
+    return fail(CTR_ERR_UNSUPPORTED, "hot_rows is not 16-byte aligned");
+  if (nnz < 0 || nnz > kMaxElems) return fail(CTR_ERR_INVALID_ARGUMENT, "bad nnz");
+  if (num_tables < 1) return fail(CTR_ERR_INVALID_ARGUMENT, "num_tables must be >= 1");
+  if (batch < 0 || (int64_t)num_tables * batch > kMaxElems)
+    return fail(CTR_ERR_INVALID_ARGUMENT, "bad batch");
+  if (batch > 0 && (!offsets || !out)) return fail(CTR_ERR_INVALID_ARGUMENT, "offsets and out are required");
+  if (nnz > 0 && !values) return fail(CTR_ERR_INVALID_ARGUMENT, "values is NULL");
+  if (out && (!aligned16(out) || out_stride_b % 4 || out_stride_t % 4 || out_stride_b < 0 ||
+              out_stride_t < 0))
+    return fail(CTR_ERR_UNSUPPORTED, "out must be 16-byte aligned with strides multiple of 4");
+  return hip_status(ctr::launch_dict_pool(values, nnz, offsets, batch, num_tables, hot_rows,
+                                          num_hot, table, num_rows, dtype == CTR_BF16, dim, out,
+                                          out_stride_b, out_stride_t, (hipStream_t)stream),
+                    "ctr_dict_embbag_fwd");
+}
+
 int32_t ctr_init_table_hash(void* table, int32_t dtype, int32_t dim, const int64_t* row_base_host,
                             int32_t num_tables, uint64_t seed, void* stream) {
   g_msg[0] = 0;

@@ -148,6 +148,17 @@ hipError_t launch_embbag_bwd(const float* grad, int64_t sb, int64_t st, const in
                              int sgd_mode, int64_t total_rows, const int64_t* uniq, float lr,
                              uint64_t seed, void* workspace, hipStream_t s);
 
+// dict.hip
+hipError_t launch_dict_build(const int64_t* keys, const int32_t* rows, const int32_t* hot_slots,
+                             int64_t n, void* slots, int64_t capacity, int32_t* status,
+                             hipStream_t s);
+hipError_t launch_dict_lookup(const int64_t* ids, int64_t n, const void* slots,
+                              int64_t capacity, int64_t* values, hipStream_t s);
+hipError_t launch_dict_pool(const int64_t* values, int64_t nnz, const int64_t* offsets,
+                            int64_t batch, int32_t num_tables, const void* hot,
+                            int64_t hot_rows, const void* cold, int64_t cold_rows, bool bf16,
+                            int dim, float* out, int64_t sb, int64_t st, hipStream_t s);
+
 // interaction.hip
 bool interaction_bf16_supported(int F, int dim, bool self);
 bool interaction_f32_supported(int F, int dim, bool self);

@@ -26,7 +26,7 @@ EXPORTED = [
     "ctr_dot_interaction_bwd", "ctr_init_table_hash", "ctr_validate_csr", "ctr_step_run",
     "ctr_step_unique", "ctr_embbag_bwd_sgd_sr", "ctr_sparse_sgd_sr", "ctr_sr_step_seed",
     "ctr_dot_interaction_self_fwd", "ctr_dot_interaction_self_bwd", "ctr_fm_interaction_fwd",
-    "ctr_fm_interaction_bwd",
+    "ctr_fm_interaction_bwd", "ctr_dict_build", "ctr_dict_lookup", "ctr_dict_embbag_fwd",
 ]
 
 CTR_STEP_POOLED_INTERACTION, CTR_STEP_BATCH_MATRIX = 0, 1
@@ -95,6 +95,10 @@ def load() -> ctypes.CDLL:
         "ctr_dot_interaction_self_bwd": (i32, [P, P, i64, i64, i32, i32, i32, P, P]),
         "ctr_fm_interaction_fwd": (i32, [P, i64, i32, i32, P, P]),
         "ctr_fm_interaction_bwd": (i32, [P, P, i64, i32, i32, P, P]),
+        "ctr_dict_build": (i32, [P, P, P, i64, P, i64, P, P]),
+        "ctr_dict_lookup": (i32, [P, i64, P, i64, P, P]),
+        "ctr_dict_embbag_fwd": (i32, [P, i64, P, i64, i32, P, i64, P, i64, i32, i32, P, i64,
+                                      i64, P]),
         "ctr_dot_interaction_fwd": (i32, [P, i64, i32, i32, i32, P, i64, P]),
         "ctr_dot_interaction_bwd": (i32, [P, P, i64, i64, i32, i32, i32, P, P]),
         "ctr_init_table_hash": (i32, [P, i32, i32, P, i32, u64, P]),
@@ -439,3 +443,71 @@ def ctr_step_run(step: CtrStep, k: int, schedule: int, main_stream=None, side_st
 def ctr_step_unique(step: CtrStep, set_index: int, stream=None) -> None:
     _check("ctr_step_unique", load().ctr_step_unique(ctypes.byref(step), set_index,
                                                      _stream(stream)))
+
+
+# ------------------------------------------------------------------ exported dictionary
+def dict_capacity(n: int, load: float = 0.5) -> int:
+    """The smallest power-of-two slot count that keeps the table at most `load` full."""
+    cap = 2
+    while cap * load < n or cap <= n:
+        cap *= 2
+    return cap
+
+
+def ctr_dict_build(keys: torch.Tensor, rows: torch.Tensor, hot_slots: Optional[torch.Tensor],
+                   capacity: int, slots: Optional[torch.Tensor] = None,
+                   status: Optional[torch.Tensor] = None, stream=None):
+    """Builds the dictionary's hash table; returns (slots uint8 [capacity*16], status int32[3])."""
+    n = keys.numel()
+    if slots is None:
+        slots = torch.empty(capacity * 16, dtype=torch.uint8, device=keys.device)
+    if status is None:
+        status = torch.empty(3, dtype=torch.int32, device=keys.device)
+    args = (_ptr(keys), _ptr(rows), _ptr(hot_slots), n, _ptr(slots), capacity, _ptr(status))
+    _run("ctr_dict_build", args, stream, False)
+    return slots, status
+
+
+def ctr_dict_lookup(ids: torch.Tensor, slots: torch.Tensor, capacity: int,
+                    values: Optional[torch.Tensor] = None, stream=None, prepare: bool = False):
+    n = ids.numel()
+    if values is None:
+        values = torch.empty(max(n, 1), dtype=torch.int64, device=ids.device)
+    args = (_ptr(ids), n, _ptr(slots), capacity, _ptr(values))
+    return _run("ctr_dict_lookup", args, stream, prepare, values)
+
+
+def _device_view(t: torch.Tensor):
+    """Device address of a GPU tensor, or of a pinned host tensor (hipHostGetDevicePointer
+    of the HIP runtime already loaded in the process; an error rather than a guess when the
+    memory is not device-mapped)."""
+    if t.is_cuda:
+        return ctypes.c_void_p(t.data_ptr())
+    if not t.is_pinned():
+        raise ValueError("a host table must be pinned memory")
+    global _hip_rt
+    if _hip_rt is None:
+        path = [ln.split()[-1] for ln in open("/proc/self/maps") if "libamdhip64" in ln][0]
+        _hip_rt = ctypes.CDLL(path)
+    dptr = ctypes.c_void_p()
+    st = _hip_rt.hipHostGetDevicePointer(ctypes.byref(dptr), ctypes.c_void_p(t.data_ptr()),
+                                         ctypes.c_uint(0))
+    if st != 0 or not dptr.value:
+        raise RuntimeError("hipHostGetDevicePointer failed (%d)" % st)
+    return dptr
+
+
+_hip_rt = None
+
+
+def ctr_dict_embbag_fwd(values: torch.Tensor, nnz: int, offsets: torch.Tensor, batch: int,
+                        num_tables: int, hot_rows: Optional[torch.Tensor], table: torch.Tensor,
+                        out: torch.Tensor, out_stride_b: int, out_stride_t: int, stream=None,
+                        prepare: bool = False):
+    """Pooled lookup over resolved values; `table` may be a pinned host tensor."""
+    num_rows, dim = table.shape
+    num_hot = 0 if hot_rows is None else hot_rows.shape[0]
+    args = (_ptr(values), nnz, _ptr(offsets), batch, num_tables, _ptr(hot_rows), num_hot,
+            _device_view(table), num_rows, _dtype_code(table), dim, _ptr(out), out_stride_b,
+            out_stride_t)
+    return _run("ctr_dict_embbag_fwd", args, stream, prepare, out)

@@ -224,6 +224,91 @@ def large(seed: int = 0, batch: int = 32768, tables: int = 64, rows: int = 4_000
                     _offsets_from_lengths(lengths), dense, grad, 0.01, "bf16")
 
 
+@dataclasses.dataclass
+class DictWorkload:
+    """Inference-side lookup from an exported sparse-embedding dictionary ("How TensorNet
+    Supercharges Sparse Feature Training on TensorFlow", "Inference Optimization": online
+    inference reads a pre-exported sparse embedding dictionary) with a hot-row HBM cache in
+    front of it (the HBM tier of a hierarchical GPU parameter server, "Tera-scale training"
+    review, hardware-aware framework figure).
+
+    Ranks r = 1, 2, ... order IDs by popularity; rank r has the raw 64-bit ID
+    key_of_rank(r), a fixed affine bijection of [1, key_space].  The dictionary holds ranks
+    1..N: dict_keys[r-1] = key_of_rank(r), stored at row dict_rows[r-1] of a table of N rows
+    (a random permutation), and ranks 1..H also sit in the HBM cache, at slot r - 1
+    (hot_slots; -1 for the others).  A query ID has a Zipf(alpha) rank over the key space,
+    so ranks above N miss the dictionary.  One ID per (sample, slot) bag."""
+
+    name: str
+    dim: int
+    dtype: str
+    batch: int
+    slots: int
+    key_space: int
+    dict_keys: np.ndarray        # int64 [N]
+    dict_rows: np.ndarray        # int32 [N]
+    hot_slots: np.ndarray        # int32 [N]
+    hot: int                     # H
+    indices: np.ndarray          # int64 [batch * slots] raw query IDs
+    offsets: np.ndarray          # int64 [batch * slots + 1]
+    table_seed: int = TABLE_SEED
+
+    @property
+    def entries(self) -> int:
+        return int(self.dict_keys.shape[0])
+
+    @property
+    def nnz(self) -> int:
+        return int(self.indices.shape[0])
+
+
+_KEY_MULT = 38_196_601_123       # odd and not a multiple of 5: coprime to 10^11
+_KEY_ADD = 12_345_678_901
+
+
+def key_of_rank(r: np.ndarray, key_space: int) -> np.ndarray:
+    """A fixed bijection of [1, key_space] (key_space = 10^11): ((r-1)*M + A) mod key_space + 1."""
+    r = np.asarray(r, dtype=object) if key_space > (1 << 31) else np.asarray(r)
+    k = ((r - 1) * _KEY_MULT + _KEY_ADD) % key_space + 1
+    return np.asarray(k, dtype=np.int64)
+
+
+def dictionary(seed: int = 0, batch: int = 65536, slots: int = 100, entries: int = 20_000_000,
+               hot: int = 2_000_000, key_space: int = 100_000_000_000,
+               alpha: float = 1.2) -> DictWorkload:
+    """The TensorNet batch shape (65,536 x 100 IDs, Zipf(1.2) over 1e11) against a dictionary
+    of the 2e7 most popular IDs (d = 32 fp32), the 2e6 hottest also cached in HBM."""
+    rng = np.random.default_rng(seed)
+    ranks = np.arange(1, entries + 1, dtype=np.int64)
+    keys = _affine_keys(ranks, key_space)
+    rows = rng.permutation(entries).astype(np.int32)                           # draw 1
+    hot_slots = np.full(entries, -1, dtype=np.int32)
+    hot_slots[:hot] = np.arange(hot, dtype=np.int32)
+    q = unbounded_zipf_capped(rng, alpha, key_space, batch * slots)            # draw 2
+    return DictWorkload("dictionary", 32, "f32", batch, slots, key_space, keys, rows,
+                        hot_slots, hot, _affine_keys(q, key_space),
+                        np.arange(batch * slots + 1, dtype=np.int64))
+
+
+def _affine_keys(ranks: np.ndarray, key_space: int) -> np.ndarray:
+    """key_of_rank without object arrays: (r-1)*M mod key_space by 32-bit halves of M."""
+    r = (np.asarray(ranks, dtype=np.int64) - 1) % key_space
+    lo, hi = _KEY_MULT & 0xFFFFFFFF, _KEY_MULT >> 32
+    # (r * (hi*2^32 + lo)) mod K = ((r*hi mod K) * 2^32 + r*lo) mod K, each product < 2^63
+    a = (r * hi) % key_space
+    a = ((a * (1 << 16)) % key_space * (1 << 16)) % key_space
+    b = ((r % key_space) * lo) % key_space if lo < (1 << 26) else _mulmod(r, lo, key_space)
+    return ((a + b + _KEY_ADD) % key_space + 1).astype(np.int64)
+
+
+def _mulmod(r: np.ndarray, m: int, k: int) -> np.ndarray:
+    """(r * m) mod k for r < k < 2^37 and m < 2^32, without overflow: m in 16-bit halves."""
+    m_lo, m_hi = m & 0xFFFF, m >> 16
+    a = (r * m_hi) % k
+    a = (a * (1 << 16)) % k
+    return (a + (r * m_lo) % k) % k
+
+
 def slice_batch(w: Workload, b: int) -> Workload:
     """The first `b` samples of every table (a bounded sample of the same batch)."""
     b = min(int(b), w.batch)

@@ -191,6 +191,29 @@ def test_interaction_variant_bad_args():
     assert lib.ctr_fm_interaction_fwd(None, 0, 3, 16, None, None) == ctr.CTR_OK   # empty batch
 
 
+def test_dictionary_bad_args():
+    lib = _lib()
+    st32 = FAKE
+    # capacity must be a power of two above n
+    assert lib.ctr_dict_build(FAKE, FAKE, None, 10, FAKE, 12, st32, None) == \
+        ctr.CTR_ERR_INVALID_ARGUMENT
+    assert lib.ctr_dict_build(FAKE, FAKE, None, 16, FAKE, 16, st32, None) == \
+        ctr.CTR_ERR_INVALID_ARGUMENT
+    assert b"capacity" in lib.ctr_last_error()
+    assert lib.ctr_dict_build(FAKE, FAKE, None, 10, MISALIGNED, 16, st32, None) == \
+        ctr.CTR_ERR_UNSUPPORTED
+    assert lib.ctr_dict_lookup(FAKE, 10, FAKE, 100, FAKE, None) == ctr.CTR_ERR_INVALID_ARGUMENT
+    assert lib.ctr_dict_lookup(FAKE, 10, None, 64, FAKE, None) == ctr.CTR_ERR_INVALID_ARGUMENT
+    p = lib.ctr_dict_embbag_fwd
+    # an empty dictionary table, a cache count without a cache, misaligned output
+    assert p(FAKE, 10, FAKE, 10, 1, None, 0, FAKE, 0, ctr.CTR_F32, 32, FAKE, 32, 0, None) == \
+        ctr.CTR_ERR_INVALID_ARGUMENT
+    assert p(FAKE, 10, FAKE, 10, 1, None, 5, FAKE, 100, ctr.CTR_F32, 32, FAKE, 32, 0, None) == \
+        ctr.CTR_ERR_INVALID_ARGUMENT
+    assert p(FAKE, 10, FAKE, 10, 1, None, 0, FAKE, 100, ctr.CTR_F32, 32, MISALIGNED, 32, 0,
+             None) == ctr.CTR_ERR_UNSUPPORTED
+
+
 def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
     monkeypatch.setattr(ctr, "LIB_PATH", str(tmp_path / "missing.so"))
     monkeypatch.setattr(ctr, "_lib", None)
