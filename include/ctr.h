@@ -182,6 +182,24 @@ int32_t ctr_embbag_bwd_sgd_sr(const float* grad, int64_t grad_stride_b, int64_t 
                               void* workspace, size_t* workspace_bytes, void* stream);
 
 /*
+ * ctr_embbag_bwd_sgd_ex -- the backward of the pooling from sorted_src, in general form:
+ *   grad: grad_dtype elements, CTR_F32 or CTR_BF16 (widened exactly; sums stay fp32),
+ *         8-byte aligned for bf16, 16-byte for fp32;
+ *   table: the SGD target as in ctr_embbag_bwd_sgd, or NULL (then only row_grads, which is
+ *         required, is written);
+ *   rounding: CTR_ROUND_NEAREST, or CTR_ROUND_STOCHASTIC with `seed` (bf16 table; see
+ *         ctr_sparse_sgd_sr).
+ * ctr_embbag_bwd_sgd and ctr_embbag_bwd_sgd_sr are this call with fp32 gradients.
+ */
+int32_t ctr_embbag_bwd_sgd_ex(const void* grad, int32_t grad_dtype, int64_t grad_stride_b,
+                              int64_t grad_stride_t, const int64_t* offsets, int64_t batch,
+                              int32_t num_tables, int64_t nnz, const int32_t* sorted_src,
+                              const int32_t* num_unique, void* table, int32_t dtype,
+                              int64_t total_rows, int32_t dim, const int64_t* uniq, float lr,
+                              int32_t rounding, uint64_t seed, float* row_grads, void* workspace,
+                              size_t* workspace_bytes, void* stream);
+
+/*
  * ctr_sparse_sgd -- update of the touched rows only ([TN] "Synchronous Architecture"):
  *   table[uniq[u], :] = round(table[uniq[u], :] - lr * row_grads[u, :])
  * for u < min(num_unique[0], capacity), computed in fp32 (one fused multiply-add) and
@@ -236,6 +254,18 @@ int32_t ctr_dot_interaction_fwd(const float* Z, int64_t batch, int32_t num_vecto
 int32_t ctr_dot_interaction_bwd(const float* Z, const float* dR, int64_t dr_stride,
                                 int64_t batch, int32_t num_vectors, int32_t dim,
                                 int32_t compute, float* dZ, void* stream);
+
+/*
+ * ctr_dot_interaction_bwd_ex -- ctr_dot_interaction_bwd (with_self = 0) or
+ * ctr_dot_interaction_self_bwd (with_self != 0), with dZ stored as dz_dtype: CTR_F32, or
+ * CTR_BF16 (nearest-even of the fp32 result; needs compute = CTR_BF16).  A bf16 dZ halves
+ * the bytes the backward of the pooling re-reads per occurrence; its consumer accumulates in
+ * fp32 (ctr_embbag_bwd_sgd_ex with grad_dtype = CTR_BF16).
+ */
+int32_t ctr_dot_interaction_bwd_ex(const float* Z, const float* dR, int64_t dr_stride,
+                                   int64_t batch, int32_t num_vectors, int32_t dim,
+                                   int32_t compute, int32_t with_self, int32_t dz_dtype,
+                                   void* dZ, void* stream);
 
 /*
  * ctr_dot_interaction_self_fwd / _self_bwd -- the pair set with self-dots, [DHEN] 3.1 ("all
@@ -382,7 +412,7 @@ typedef struct {
   float* Z;
   float* R;
   const float* dR;
-  float* dZ;
+  void* dZ;                       /* fp32 or bf16, see grad_dtype */
   float* E;
   float* out;
   const float* dout;
@@ -400,6 +430,8 @@ typedef struct {
   int32_t rounding;               /* CTR_ROUND_NEAREST, or CTR_ROUND_STOCHASTIC (bf16 table):
                                      step k updates with seed ctr_sr_step_seed(sr_seed, k) */
   uint64_t sr_seed;
+  int32_t grad_dtype;             /* element type of dZ: CTR_F32, or CTR_BF16 (compute must be
+                                     CTR_BF16; dZ then holds bf16 [batch, F, dim]) */
 } ctr_step_t;
 
 /*

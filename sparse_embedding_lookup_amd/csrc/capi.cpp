@@ -206,15 +206,15 @@ int32_t ctr_embbag_bwd(const float* grad, int64_t grad_stride_b, int64_t grad_st
       grad_stride_t % 4)
     return fail(CTR_ERR_UNSUPPORTED, "grad/row_grads must be 16-byte aligned, strides multiple of 4");
   if (!aligned16(workspace)) return fail(CTR_ERR_UNSUPPORTED, "workspace is not 16-byte aligned");
-  return hip_status(ctr::launch_embbag_bwd(grad, grad_stride_b, grad_stride_t, offsets, batch,
-                                           num_tables, dim, nnz, perm, inverse,
+  return hip_status(ctr::launch_embbag_bwd(grad, false, grad_stride_b, grad_stride_t, offsets,
+                                           batch, num_tables, dim, nnz, perm, inverse,
                                            reinterpret_cast<const int4*>(sorted_src), num_unique,
                                            row_grads, nullptr, 0, 0, nullptr, 0.f, 0, workspace,
                                            (hipStream_t)stream),
                     "ctr_embbag_bwd");
 }
 
-static int32_t embbag_bwd_sgd_common(const float* grad, int64_t grad_stride_b,
+static int32_t embbag_bwd_sgd_common(const void* grad, bool grad_bf16, int64_t grad_stride_b,
                                      int64_t grad_stride_t, const int64_t* offsets,
                                      int64_t batch, int32_t num_tables, int64_t nnz,
                                      const int32_t* sorted_src, const int32_t* num_unique,
@@ -224,8 +224,14 @@ static int32_t embbag_bwd_sgd_common(const float* grad, int64_t grad_stride_b,
                                      uint64_t seed, void* stream, const char* name) {
   g_msg[0] = 0;
   if (!workspace_bytes) return fail(CTR_ERR_INVALID_ARGUMENT, "workspace_bytes is NULL");
-  int32_t st = check_table(table, dtype, total_rows, dim);
-  if (st) return st;
+  if (table) {
+    int32_t st = check_table(table, dtype, total_rows, dim);
+    if (st) return st;
+  } else {
+    if (dim <= 0) return fail(CTR_ERR_INVALID_ARGUMENT, "dim must be positive");
+    if (dim % 4) return fail(CTR_ERR_UNSUPPORTED, "dim %d is not a multiple of 4", dim);
+    if (stochastic) return fail(CTR_ERR_INVALID_ARGUMENT, "stochastic rounding needs a table");
+  }
   if (stochastic && dtype != CTR_BF16)
     return fail(CTR_ERR_UNSUPPORTED, "stochastic rounding needs a CTR_BF16 table");
   if (dim > 1024) return fail(CTR_ERR_UNSUPPORTED, "dim %d above 1024", dim);
@@ -243,25 +249,52 @@ static int32_t embbag_bwd_sgd_common(const float* grad, int64_t grad_stride_b,
   if (*workspace_bytes < need)
     return fail(CTR_ERR_WORKSPACE_TOO_SMALL, "workspace %zu < %zu bytes", *workspace_bytes, need);
   if (!offsets || !num_unique) return fail(CTR_ERR_INVALID_ARGUMENT, "offsets and num_unique are required");
-  if (nnz > 0 && (!grad || !sorted_src || !uniq))
+  if (nnz > 0 && (!grad || !sorted_src || (table && !uniq)))
     return fail(CTR_ERR_INVALID_ARGUMENT, "grad, sorted_src and uniq are required");
+  if (!table && !row_grads)
+    return fail(CTR_ERR_INVALID_ARGUMENT, "without a table, row_grads is required");
   if (!std::isfinite(lr)) return fail(CTR_ERR_INVALID_ARGUMENT, "lr is not finite");
   if (grad_stride_b < 0 || grad_stride_t < 0)
     return fail(CTR_ERR_INVALID_ARGUMENT, "negative gradient stride");
-  if ((grad && !aligned16(grad)) || (row_grads && !aligned16(row_grads)) || grad_stride_b % 4 ||
-      grad_stride_t % 4)
-    return fail(CTR_ERR_UNSUPPORTED, "grad/row_grads must be 16-byte aligned, strides multiple of 4");
+  // bf16 rows are read 8 bytes per 4 columns, fp32 rows 16 bytes
+  const uintptr_t galign = grad_bf16 ? 7u : 15u;
+  if ((grad && (reinterpret_cast<uintptr_t>(grad) & galign)) ||
+      (row_grads && !aligned16(row_grads)) || grad_stride_b % 4 || grad_stride_t % 4)
+    return fail(CTR_ERR_UNSUPPORTED,
+                "grad must be %d-byte aligned, row_grads 16-byte, strides multiple of 4",
+                grad_bf16 ? 8 : 16);
   if (reinterpret_cast<uintptr_t>(sorted_src) & 15u)
     return fail(CTR_ERR_UNSUPPORTED, "sorted_src is not 16-byte aligned");
   if (!aligned16(workspace)) return fail(CTR_ERR_UNSUPPORTED, "workspace is not 16-byte aligned");
-  return hip_status(ctr::launch_embbag_bwd(grad, grad_stride_b, grad_stride_t, offsets, batch,
-                                           num_tables, dim, nnz, nullptr, nullptr,
-                                           reinterpret_cast<const int4*>(sorted_src), num_unique,
-                                           row_grads, table,
-                                           dtype == CTR_BF16 ? (stochastic ? 3 : 2) : 1,
-                                           total_rows, uniq, lr, seed, workspace,
-                                           (hipStream_t)stream),
+  const int mode = !table ? 0 : dtype == CTR_BF16 ? (stochastic ? 3 : 2) : 1;
+  return hip_status(ctr::launch_embbag_bwd(grad, grad_bf16, grad_stride_b, grad_stride_t,
+                                           offsets, batch, num_tables, dim, nnz, nullptr,
+                                           nullptr, reinterpret_cast<const int4*>(sorted_src),
+                                           num_unique, row_grads, table, mode, total_rows, uniq,
+                                           lr, seed, workspace, (hipStream_t)stream),
                     name);
+}
+
+int32_t ctr_embbag_bwd_sgd_ex(const void* grad, int32_t grad_dtype, int64_t grad_stride_b,
+                              int64_t grad_stride_t, const int64_t* offsets, int64_t batch,
+                              int32_t num_tables, int64_t nnz, const int32_t* sorted_src,
+                              const int32_t* num_unique, void* table, int32_t dtype,
+                              int64_t total_rows, int32_t dim, const int64_t* uniq, float lr,
+                              int32_t rounding, uint64_t seed, float* row_grads, void* workspace,
+                              size_t* workspace_bytes, void* stream) {
+  if (grad_dtype != CTR_F32 && grad_dtype != CTR_BF16) {
+    g_msg[0] = 0;
+    return fail(CTR_ERR_INVALID_ARGUMENT, "grad_dtype %d is not CTR_F32 or CTR_BF16", grad_dtype);
+  }
+  if (rounding != CTR_ROUND_NEAREST && rounding != CTR_ROUND_STOCHASTIC) {
+    g_msg[0] = 0;
+    return fail(CTR_ERR_INVALID_ARGUMENT, "unknown rounding %d", rounding);
+  }
+  return embbag_bwd_sgd_common(grad, grad_dtype == CTR_BF16, grad_stride_b, grad_stride_t,
+                               offsets, batch, num_tables, nnz, sorted_src, num_unique, table,
+                               dtype, total_rows, dim, uniq, lr, row_grads, workspace,
+                               workspace_bytes, rounding == CTR_ROUND_STOCHASTIC, seed, stream,
+                               "ctr_embbag_bwd_sgd_ex");
 }
 
 int32_t ctr_embbag_bwd_sgd(const float* grad, int64_t grad_stride_b, int64_t grad_stride_t,
@@ -270,10 +303,14 @@ int32_t ctr_embbag_bwd_sgd(const float* grad, int64_t grad_stride_b, int64_t gra
                            void* table, int32_t dtype, int64_t total_rows, int32_t dim,
                            const int64_t* uniq, float lr, float* row_grads, void* workspace,
                            size_t* workspace_bytes, void* stream) {
-  return embbag_bwd_sgd_common(grad, grad_stride_b, grad_stride_t, offsets, batch, num_tables,
-                               nnz, sorted_src, num_unique, table, dtype, total_rows, dim, uniq,
-                               lr, row_grads, workspace, workspace_bytes, false, 0, stream,
-                               "ctr_embbag_bwd_sgd");
+  if (!table) {
+    g_msg[0] = 0;
+    return fail(CTR_ERR_INVALID_ARGUMENT, "table is NULL");
+  }
+  return embbag_bwd_sgd_common(grad, false, grad_stride_b, grad_stride_t, offsets, batch,
+                               num_tables, nnz, sorted_src, num_unique, table, dtype, total_rows,
+                               dim, uniq, lr, row_grads, workspace, workspace_bytes, false, 0,
+                               stream, "ctr_embbag_bwd_sgd");
 }
 
 int32_t ctr_embbag_bwd_sgd_sr(const float* grad, int64_t grad_stride_b, int64_t grad_stride_t,
@@ -282,10 +319,14 @@ int32_t ctr_embbag_bwd_sgd_sr(const float* grad, int64_t grad_stride_b, int64_t 
                               void* table, int32_t dtype, int64_t total_rows, int32_t dim,
                               const int64_t* uniq, float lr, uint64_t seed, float* row_grads,
                               void* workspace, size_t* workspace_bytes, void* stream) {
-  return embbag_bwd_sgd_common(grad, grad_stride_b, grad_stride_t, offsets, batch, num_tables,
-                               nnz, sorted_src, num_unique, table, dtype, total_rows, dim, uniq,
-                               lr, row_grads, workspace, workspace_bytes, true, seed, stream,
-                               "ctr_embbag_bwd_sgd_sr");
+  if (!table) {
+    g_msg[0] = 0;
+    return fail(CTR_ERR_INVALID_ARGUMENT, "table is NULL");
+  }
+  return embbag_bwd_sgd_common(grad, false, grad_stride_b, grad_stride_t, offsets, batch,
+                               num_tables, nnz, sorted_src, num_unique, table, dtype, total_rows,
+                               dim, uniq, lr, row_grads, workspace, workspace_bytes, true, seed,
+                               stream, "ctr_embbag_bwd_sgd_sr");
 }
 
 static int32_t sparse_sgd_common(void* table, int32_t dtype, int64_t total_rows, int32_t dim,
@@ -364,15 +405,32 @@ static int32_t interaction_fwd_common(const float* Z, int64_t batch, int32_t F, 
 
 static int32_t interaction_bwd_common(const float* Z, const float* dR, int64_t dr_stride,
                                       int64_t batch, int32_t F, int32_t dim, int32_t compute,
-                                      bool self, float* dZ, void* stream, const char* name) {
+                                      bool self, bool dz_bf16, void* dZ, void* stream,
+                                      const char* name) {
   g_msg[0] = 0;
-  int32_t st = check_interaction(Z, batch, F, dim, compute, self, dZ, dr_stride);
+  int32_t st = check_interaction(Z, batch, F, dim, compute, self, static_cast<const float*>(dZ),
+                                 dr_stride);
   if (st) return st;
   if (batch > 0 && !dR) return fail(CTR_ERR_INVALID_ARGUMENT, "dR is NULL");
+  if (dz_bf16 && compute != CTR_BF16)
+    return fail(CTR_ERR_UNSUPPORTED, "a bf16 dZ needs compute = CTR_BF16");
   return hip_status(ctr::launch_interaction_bwd(Z, dR, dr_stride, batch, F, dim,
-                                                compute == CTR_BF16, self, dZ,
+                                                compute == CTR_BF16, self, dz_bf16, dZ,
                                                 (hipStream_t)stream),
                     name);
+}
+
+int32_t ctr_dot_interaction_bwd_ex(const float* Z, const float* dR, int64_t dr_stride,
+                                   int64_t batch, int32_t num_vectors, int32_t dim,
+                                   int32_t compute, int32_t with_self, int32_t dz_dtype,
+                                   void* dZ, void* stream) {
+  if (dz_dtype != CTR_F32 && dz_dtype != CTR_BF16) {
+    g_msg[0] = 0;
+    return fail(CTR_ERR_INVALID_ARGUMENT, "dz_dtype %d is not CTR_F32 or CTR_BF16", dz_dtype);
+  }
+  return interaction_bwd_common(Z, dR, dr_stride, batch, num_vectors, dim, compute,
+                                with_self != 0, dz_dtype == CTR_BF16, dZ, stream,
+                                "ctr_dot_interaction_bwd_ex");
 }
 
 int32_t ctr_dot_interaction_fwd(const float* Z, int64_t batch, int32_t num_vectors, int32_t dim,
@@ -384,8 +442,8 @@ int32_t ctr_dot_interaction_fwd(const float* Z, int64_t batch, int32_t num_vecto
 int32_t ctr_dot_interaction_bwd(const float* Z, const float* dR, int64_t dr_stride,
                                 int64_t batch, int32_t num_vectors, int32_t dim, int32_t compute,
                                 float* dZ, void* stream) {
-  return interaction_bwd_common(Z, dR, dr_stride, batch, num_vectors, dim, compute, false, dZ,
-                                stream, "ctr_dot_interaction_bwd");
+  return interaction_bwd_common(Z, dR, dr_stride, batch, num_vectors, dim, compute, false, false,
+                                dZ, stream, "ctr_dot_interaction_bwd");
 }
 
 int32_t ctr_dot_interaction_self_fwd(const float* Z, int64_t batch, int32_t num_vectors,
@@ -398,8 +456,8 @@ int32_t ctr_dot_interaction_self_fwd(const float* Z, int64_t batch, int32_t num_
 int32_t ctr_dot_interaction_self_bwd(const float* Z, const float* dR, int64_t dr_stride,
                                      int64_t batch, int32_t num_vectors, int32_t dim,
                                      int32_t compute, float* dZ, void* stream) {
-  return interaction_bwd_common(Z, dR, dr_stride, batch, num_vectors, dim, compute, true, dZ,
-                                stream, "ctr_dot_interaction_self_bwd");
+  return interaction_bwd_common(Z, dR, dr_stride, batch, num_vectors, dim, compute, true, false,
+                                dZ, stream, "ctr_dot_interaction_self_bwd");
 }
 
 static int32_t check_fm(const float* Z, int64_t batch, int32_t F, int32_t dim, const float* a,

@@ -141,7 +141,8 @@ hipError_t launch_validate_csr(const void* idx, bool idx64, int64_t nnz, const i
 
 // segreduce.hip
 size_t embbag_bwd_workspace_bytes(int64_t nnz, int dim);
-hipError_t launch_embbag_bwd(const float* grad, int64_t sb, int64_t st, const int64_t* offsets,
+hipError_t launch_embbag_bwd(const void* grad, bool grad_bf16, int64_t sb, int64_t st,
+                             const int64_t* offsets,
                              int64_t batch, int32_t num_tables, int dim, int64_t nnz,
                              const int32_t* perm, const int32_t* inverse, const int4* sorted_src,
                              const int32_t* num_unique, float* row_grads, void* table,
@@ -165,8 +166,8 @@ bool interaction_f32_supported(int F, int dim, bool self);
 hipError_t launch_interaction_fwd(const float* Z, int64_t batch, int F, int dim, bool bf16,
                                   bool self, float* R, int64_t r_stride, hipStream_t s);
 hipError_t launch_interaction_bwd(const float* Z, const float* dR, int64_t dr_stride,
-                                  int64_t batch, int F, int dim, bool bf16, bool self, float* dZ,
-                                  hipStream_t s);
+                                  int64_t batch, int F, int dim, bool bf16, bool self,
+                                  bool out_bf16, void* dZ, hipStream_t s);
 hipError_t launch_fm_fwd(const float* Z, int64_t batch, int F, int dim, float* out,
                          hipStream_t s);
 hipError_t launch_fm_bwd(const float* Z, const float* dout, int64_t batch, int F, int dim,

@@ -14,7 +14,8 @@
 //     v_mfma_f32_32x32x16_bf16 over the lower-triangle 32x32 tiles, operands rounded to
 //     bf16 nearest-even and kept in registers, fp32 accumulation, only i > j written.
 //     Backward: dZ = S Z with S the symmetric zero-diagonal matrix of pair gradients
-//     (staged in LDS), A = S tiles, B = Z column slabs, fp32 accumulation.
+//     (staged in LDS), A = S tiles, B = Z column slabs, fp32 accumulation; dZ stored as
+//     fp32, or rounded to bf16 for a bf16 backward (half the bytes its consumer re-reads).
 // Both paths are memory-bound on the 8 TB/s HBM: the arithmetic intensity is 6-14 flop/B.
 //
 // Variants ("DHEN" notes, 3.1 and Solution 2):
@@ -375,10 +376,11 @@ __global__ __launch_bounds__(kThreads) void interaction_fwd_mfma_kernel(
 // One wave per sample; WPB samples per block; LDS holds each sample's pair gradients.
 // For each 32-row block of S (A operand, built once from LDS) and each 32-column slab of Z
 // (B operand, re-read per row block from L1/L2), 2*FB MFMAs give a 32x32 block of dZ.
-template <int FB, int KS, bool SELF>
+// OUTB: dZ is stored as bf16 (nearest-even of the fp32 accumulator) instead of fp32.
+template <int FB, int KS, bool SELF, bool OUTB>
 __global__ __launch_bounds__(kThreads) void interaction_bwd_mfma_kernel(
     const float* __restrict__ Z, const float* __restrict__ dR, int64_t dr_stride,
-    int64_t batch, int F, int wpb, float* __restrict__ dZ) {
+    int64_t batch, int F, int wpb, void* __restrict__ dZ) {
   constexpr int FKS = 2 * FB;             // k-steps of 16 over the padded F
   constexpr int dim = KS * 16;
   extern __shared__ float sp_all[];
@@ -457,7 +459,10 @@ __global__ __launch_bounds__(kThreads) void interaction_bwd_mfma_kernel(
         if (io < F) {
           float val = acc[v];
           if (io == 0) val += dR[b * dr_stride + n];
-          dZ[(b * F + io) * dim + n] = val;
+          if constexpr (OUTB)
+            static_cast<__bf16*>(dZ)[(b * F + io) * dim + n] = (__bf16)val;
+          else
+            static_cast<float*>(dZ)[(b * F + io) * dim + n] = val;
         }
       }
     }
@@ -612,9 +617,10 @@ hipError_t interaction_fwd(const float* Z, int64_t batch, int F, int dim, bool b
 
 template <bool SELF>
 hipError_t interaction_bwd(const float* Z, const float* dR, int64_t dr_stride, int64_t batch,
-                           int F, int dim, bool bf16, float* dZ, hipStream_t s) {
+                           int F, int dim, bool bf16, bool out_bf16, void* dZv, hipStream_t s) {
   if (batch == 0) return hipSuccess;
   const int P = num_pairs<SELF>(F);
+  float* dZ = static_cast<float*>(dZv);
   if (!bf16) {
     if (lanes_shape(F, dim, SELF)) {
       const int L_ = dim / 4;
@@ -637,14 +643,24 @@ hipError_t interaction_bwd(const float* Z, const float* dR, int64_t dr_stride, i
   const size_t lds = (size_t)wpb * (P + 1) * sizeof(float);
   const int64_t blocks = (batch + wpb - 1) / wpb;
   const int KS = dim / 16;
+#define CTR_BWD_MFMA(KS_)                                                                      \
+  do {                                                                                         \
+    if (out_bf16)                                                                              \
+      interaction_bwd_mfma_kernel<FB, KS_, SELF, true><<<(unsigned)blocks, kThreads, lds, s>>>( \
+          Z, dR, dr_stride, batch, F, wpb, dZv);                                               \
+    else                                                                                       \
+      interaction_bwd_mfma_kernel<FB, KS_, SELF, false><<<(unsigned)blocks, kThreads, lds, s>>>( \
+          Z, dR, dr_stride, batch, F, wpb, dZv);                                               \
+  } while (0)
   CTR_FB_DISPATCH(FB, {
     switch (KS) {
-      case 1: interaction_bwd_mfma_kernel<FB, 1, SELF><<<(unsigned)blocks, kThreads, lds, s>>>(Z, dR, dr_stride, batch, F, wpb, dZ); break;
-      case 2: interaction_bwd_mfma_kernel<FB, 2, SELF><<<(unsigned)blocks, kThreads, lds, s>>>(Z, dR, dr_stride, batch, F, wpb, dZ); break;
-      case 4: interaction_bwd_mfma_kernel<FB, 4, SELF><<<(unsigned)blocks, kThreads, lds, s>>>(Z, dR, dr_stride, batch, F, wpb, dZ); break;
-      default: interaction_bwd_mfma_kernel<FB, 8, SELF><<<(unsigned)blocks, kThreads, lds, s>>>(Z, dR, dr_stride, batch, F, wpb, dZ); break;
+      case 1: CTR_BWD_MFMA(1); break;
+      case 2: CTR_BWD_MFMA(2); break;
+      case 4: CTR_BWD_MFMA(4); break;
+      default: CTR_BWD_MFMA(8); break;
     }
   });
+#undef CTR_BWD_MFMA
   return hipGetLastError();
 }
 
@@ -657,10 +673,10 @@ hipError_t launch_interaction_fwd(const float* Z, int64_t batch, int F, int dim,
 }
 
 hipError_t launch_interaction_bwd(const float* Z, const float* dR, int64_t dr_stride,
-                                  int64_t batch, int F, int dim, bool bf16, bool self, float* dZ,
-                                  hipStream_t s) {
-  return self ? interaction_bwd<true>(Z, dR, dr_stride, batch, F, dim, bf16, dZ, s)
-              : interaction_bwd<false>(Z, dR, dr_stride, batch, F, dim, bf16, dZ, s);
+                                  int64_t batch, int F, int dim, bool bf16, bool self,
+                                  bool out_bf16, void* dZ, hipStream_t s) {
+  return self ? interaction_bwd<true>(Z, dR, dr_stride, batch, F, dim, bf16, out_bf16, dZ, s)
+              : interaction_bwd<false>(Z, dR, dr_stride, batch, F, dim, bf16, out_bf16, dZ, s);
 }
 
 hipError_t launch_fm_fwd(const float* Z, int64_t batch, int F, int dim, float* out,

@@ -64,12 +64,37 @@ __global__ __launch_bounds__(kThreads) void seg_src_kernel(const int32_t* __rest
   src[p] = r;
 }
 
-struct L0Source {
+// Level-0 entries: the sorted (u, bag, key) quadruples, and the per-bag gradient rows they
+// point at, fp32 or bf16 (GB; widened exactly).  Offsets are in elements.
+template <bool GB>
+struct L0SourceT {
   const int4* src;
-  const float* grad;
+  const void* grad;
   int64_t sb, st, batch, num_bags;
   __device__ __forceinline__ int32_t key(int64_t p) const { return src[p].x; }
+  // Four consecutive gradient values at element offset `off` (a multiple of 4), loaded raw
+  // (8 bytes of bf16, or 16 of fp32) and widened only where they are added, so that a
+  // slot's loads issue together and bf16 rows stay packed in registers until then.
+  using Raw = typename std::conditional<GB, uint2, float4>::type;
+  __device__ __forceinline__ Raw load_raw(int64_t off) const {
+    if constexpr (GB)
+      return *reinterpret_cast<const uint2*>(static_cast<const __bf16*>(grad) + off);
+    else
+      return *reinterpret_cast<const float4*>(static_cast<const float*>(grad) + off);
+  }
+  static __device__ __forceinline__ Raw zero_raw() {
+    if constexpr (GB) return make_uint2(0u, 0u);
+    else return make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+  static __device__ __forceinline__ float4 widen(const Raw& r) {
+    if constexpr (GB)
+      return make_float4(bf16_lo(r.x), bf16_hi(r.x), bf16_lo(r.y), bf16_hi(r.y));
+    else
+      return r;
+  }
 };
+using L0Source = L0SourceT<false>;
+using L0SourceB = L0SourceT<true>;
 
 struct LnSource {
   const int32_t* keys;
@@ -192,8 +217,8 @@ struct PendingRow {
 // differs; a piece whose key equals the key just before the slot began earlier (sorted
 // keys), and one whose key equals the key just after continues later: those two go to LDS
 // for the join, every other piece is complete and is written out (and applied) here.
-template <int G, int MODE>
-__device__ __forceinline__ void slot_prefetched(const L0Source& S, int64_t q0, int64_t q1,
+template <int G, int MODE, typename Src>
+__device__ __forceinline__ void slot_prefetched(const Src& S, int64_t q0, int64_t q1,
                                                 int64_t n, int dim, int64_t capacity,
                                                 float* __restrict__ row_grads,
                                                 const SgdTarget& sgd, SegSmem<G, 1>& sm, int slot,
@@ -227,16 +252,15 @@ __device__ __forceinline__ void slot_prefetched(const L0Source& S, int64_t q0, i
 
   // all gradient rows of the slot
   int32_t kk[kPerSlot];
-  float4 rv[kPerSlot];
+  typename Src::Raw rv[kPerSlot];
 #pragma unroll
   for (int e = 0; e < kPerSlot; ++e) {
     kk[e] = __shfl(ekey[e / G], lane0 + (e % G), 64);
     uint32_t bag = (uint32_t)__shfl(ebag[e / G], lane0 + (e % G), 64);
     if ((int64_t)bag >= S.num_bags) bag = 0;
     const uint32_t t = bag / (uint32_t)S.batch, b = bag - t * (uint32_t)S.batch;
-    const float* rp = S.grad + (int64_t)b * S.sb + (int64_t)t * S.st;
-    rv[e] = (e < len && col_ok && kk[e] != -1) ? *reinterpret_cast<const float4*>(rp + c)
-                                               : make_float4(0.f, 0.f, 0.f, 0.f);
+    const int64_t goff = (int64_t)b * S.sb + (int64_t)t * S.st;
+    rv[e] = (e < len && col_ok && kk[e] != -1) ? S.load_raw(goff + c) : Src::zero_raw();
   }
 
   // table rows of the segments completed inside the slot, and of the last piece
@@ -270,10 +294,11 @@ __device__ __forceinline__ void slot_prefetched(const L0Source& S, int64_t q0, i
 #pragma unroll
   for (int e = 0; e < kPerSlot; ++e) {
     if (e < len) {
-      acc.x += rv[e].x;
-      acc.y += rv[e].y;
-      acc.z += rv[e].z;
-      acc.w += rv[e].w;
+      const float4 x = Src::widen(rv[e]);
+      acc.x += x.x;
+      acc.y += x.y;
+      acc.z += x.z;
+      acc.w += x.w;
       const int32_t k = kk[e];
       const int32_t nx = (e + 1 < len) ? kk[e + 1 < kPerSlot ? e + 1 : e] : ka;
       if (nx != k) {                           // the piece ends at e
@@ -366,7 +391,7 @@ __device__ __forceinline__ void reduce_chunk(
   PendingRow<MODE> pend;
   if constexpr (L0 && VPL == 1) {
     if (q0 < n)
-      slot_prefetched<G, MODE>(S, q0, q1, n, dim, capacity, row_grads, sgd, sm, slot, lane,
+      slot_prefetched<G, MODE, Src>(S, q0, q1, n, dim, capacity, row_grads, sgd, sm, slot, lane,
                                fkey, fcont, lkey, pend);
   } else if (q0 < n) {
     // Prefetch the slot's entries cooperatively: entry e is loaded by lane e % G of the slot
@@ -407,13 +432,14 @@ __device__ __forceinline__ void reduce_chunk(
       for (int u = 0; u < kBatch; ++u) {
         const int e = b0 + u;
         const int64_t p = q0 + e;
-        const float* rp = nullptr;
+        int64_t goff = 0;                 // L0: element offset of the bag's gradient row
+        const float* rp = nullptr;        // carries: the carry row
         kk[u] = __shfl(ekey[e / G], lane0 + (e % G), 64);
         if constexpr (L0) {
           int64_t bag = __shfl(ebag[e / G], lane0 + (e % G), 64);
           if (bag < 0 || bag >= S.num_bags) bag = 0;
           const int64_t t = bag / S.batch, b = bag - t * S.batch;
-          rp = S.grad + b * S.sb + t * S.st;
+          goff = b * S.sb + t * S.st;
         } else {
           rp = S.rows + p * (int64_t)S.dim;
         }
@@ -421,10 +447,14 @@ __device__ __forceinline__ void reduce_chunk(
         for (int a = 0; a < VPL; ++a) {
           const int c = col(a);
           // carry rows load without waiting for their key (empty entries are skipped below)
-          if (p < q1 && c < dim && (!L0 || kk[u] != -1))
-            rv[u][a] = *reinterpret_cast<const float4*>(rp + c);
-          else
+          if (p < q1 && c < dim && (!L0 || kk[u] != -1)) {
+            if constexpr (L0)
+              rv[u][a] = Src::widen(S.load_raw(goff + c));
+            else
+              rv[u][a] = *reinterpret_cast<const float4*>(rp + c);
+          } else {
             rv[u][a] = make_float4(0.f, 0.f, 0.f, 0.f);
+          }
         }
       }
 #pragma unroll
@@ -650,8 +680,8 @@ size_t embbag_bwd_workspace_bytes(int64_t nnz, int dim) { return carve(nullptr, 
     }                                                                       \
   } while (0)
 
-template <int MODE>
-static void segreduce_levels(const L0Source& s0, int64_t nnz, int dim, float* row_grads,
+template <int MODE, typename L0S>
+static void segreduce_levels(const L0S& s0, int64_t nnz, int dim, float* row_grads,
                              const SgdTarget& sgd, BwdWs& w, hipStream_t s) {
   const RowGeom rg = row_geom(dim / 4);
   const int64_t chunk = chunk_positions(dim);
@@ -659,7 +689,7 @@ static void segreduce_levels(const L0Source& s0, int64_t nnz, int dim, float* ro
     int64_t len = nnz;
     int64_t blocks = (len + chunk - 1) / chunk;
     int cur = 0;
-    segreduce_kernel<true, G, VPL, MODE, L0Source><<<(unsigned)blocks, kThreads, 0, s>>>(
+    segreduce_kernel<true, G, VPL, MODE, L0S><<<(unsigned)blocks, kThreads, 0, s>>>(
         s0, len, dim, nnz, row_grads, sgd, blocks > 1 ? w.ckeys[cur] : nullptr, w.crows[cur],
         w.ticket, nullptr);
     while (blocks > 1) {
@@ -677,7 +707,8 @@ static void segreduce_levels(const L0Source& s0, int64_t nnz, int dim, float* ro
   });
 }
 
-hipError_t launch_embbag_bwd(const float* grad, int64_t sb, int64_t st, const int64_t* offsets,
+hipError_t launch_embbag_bwd(const void* grad, bool grad_bf16, int64_t sb, int64_t st,
+                             const int64_t* offsets,
                              int64_t batch, int32_t num_tables, int dim, int64_t nnz,
                              const int32_t* perm, const int32_t* inverse, const int4* sorted_src,
                              const int32_t* num_unique, float* row_grads, void* table,
@@ -699,17 +730,23 @@ hipError_t launch_embbag_bwd(const float* grad, int64_t sb, int64_t st, const in
     src = w.src;
   }
 
-  L0Source s0{src, grad, sb, st, batch, num_bags};
   SgdTarget sgd{static_cast<char*>(table), total_rows,
                 (int64_t)dim * (sgd_mode >= 2 ? 2 : 4), uniq, lr, seed};
-  if (sgd_mode == 1)
-    segreduce_levels<1>(s0, nnz, dim, row_grads, sgd, w, s);
-  else if (sgd_mode == 2)
-    segreduce_levels<2>(s0, nnz, dim, row_grads, sgd, w, s);
-  else if (sgd_mode == 3)
-    segreduce_levels<3>(s0, nnz, dim, row_grads, sgd, w, s);
+  auto levels = [&](const auto& s0) {
+    using S0 = std::decay_t<decltype(s0)>;
+    if (sgd_mode == 1)
+      segreduce_levels<1, S0>(s0, nnz, dim, row_grads, sgd, w, s);
+    else if (sgd_mode == 2)
+      segreduce_levels<2, S0>(s0, nnz, dim, row_grads, sgd, w, s);
+    else if (sgd_mode == 3)
+      segreduce_levels<3, S0>(s0, nnz, dim, row_grads, sgd, w, s);
+    else
+      segreduce_levels<0, S0>(s0, nnz, dim, row_grads, sgd, w, s);
+  };
+  if (grad_bf16)
+    levels(L0SourceB{src, grad, sb, st, batch, num_bags});
   else
-    segreduce_levels<0>(s0, nnz, dim, row_grads, sgd, w, s);
+    levels(L0Source{src, grad, sb, st, batch, num_bags});
   return hipGetLastError();
 }
 

@@ -96,8 +96,8 @@ int32_t interaction_part(const ctr_step_t* d, hipStream_t s) {
   const int64_t F = (int64_t)d->num_tables + 1;
   CTR_TRY(ctr_dot_interaction_fwd(d->Z, d->batch, (int32_t)F, d->dim, d->compute, d->R,
                                   d->dim + F * (F - 1) / 2, s));
-  return ctr_dot_interaction_bwd(d->Z, d->dR, d->dim + F * (F - 1) / 2, d->batch, (int32_t)F,
-                                 d->dim, d->compute, d->dZ, s);
+  return ctr_dot_interaction_bwd_ex(d->Z, d->dR, d->dim + F * (F - 1) / 2, d->batch,
+                                    (int32_t)F, d->dim, d->compute, 0, d->grad_dtype, d->dZ, s);
 }
 
 // The backward with the SGD update of the touched rows.
@@ -105,20 +105,22 @@ int32_t sgd_part(const ctr_step_t* d, int set, int64_t k, hipStream_t s) {
   const int64_t F = (int64_t)d->num_tables + 1;
   size_t wsb = d->ws_bwd_bytes;
   const bool pooled = d->kind == CTR_STEP_POOLED_INTERACTION;
-  const float* grad = pooled ? d->dZ + d->dim : d->dout;
+  // dZ[:, 1:, :] of the pooled step (fp32 or bf16 elements), or dout
+  const size_t esz = (pooled && d->grad_dtype == CTR_BF16) ? 2 : 4;
+  const void* grad = pooled ? static_cast<const void*>(static_cast<const char*>(d->dZ) +
+                                                       (size_t)d->dim * esz)
+                            : static_cast<const void*>(d->dout);
+  const int32_t gdt = pooled ? d->grad_dtype : CTR_F32;
   const int64_t sb = pooled ? F * d->dim : d->dim;
   const int64_t st = pooled ? d->dim : 0;
   const int64_t batch = pooled ? d->batch : d->nnz;
   const int32_t tables = pooled ? d->num_tables : 1;
-  if (d->rounding == CTR_ROUND_STOCHASTIC)
-    return ctr_embbag_bwd_sgd_sr(grad, sb, st, d->offsets, batch, tables, d->nnz,
-                                 d->sorted_src[set], d->num_unique[set], d->table, d->dtype,
-                                 d->total_rows, d->dim, d->uniq[set], d->lr,
-                                 ctr_sr_step_seed(d->sr_seed, k), d->row_grads, d->ws_bwd, &wsb,
-                                 s);
-  return ctr_embbag_bwd_sgd(grad, sb, st, d->offsets, batch, tables, d->nnz, d->sorted_src[set],
-                            d->num_unique[set], d->table, d->dtype, d->total_rows, d->dim,
-                            d->uniq[set], d->lr, d->row_grads, d->ws_bwd, &wsb, s);
+  const bool sr = d->rounding == CTR_ROUND_STOCHASTIC;
+  return ctr_embbag_bwd_sgd_ex(grad, gdt, sb, st, d->offsets, batch, tables, d->nnz,
+                               d->sorted_src[set], d->num_unique[set], d->table, d->dtype,
+                               d->total_rows, d->dim, d->uniq[set], d->lr, d->rounding,
+                               sr ? ctr_sr_step_seed(d->sr_seed, k) : 0, d->row_grads, d->ws_bwd,
+                               &wsb, s);
 }
 
 }  // namespace
@@ -142,6 +144,7 @@ int32_t ctr_step_run(const ctr_step_t* d, int64_t k, int32_t schedule, void* mai
   if (k < 0) return invalid("step index k < 0");
   if (d->rounding != CTR_ROUND_NEAREST && d->rounding != CTR_ROUND_STOCHASTIC)
     return invalid("unknown rounding");
+  if (d->grad_dtype != CTR_F32 && d->grad_dtype != CTR_BF16) return invalid("unknown grad_dtype");
   if (schedule < CTR_SCHEDULE_SERIAL || schedule > CTR_SCHEDULE_PIPELINED_OVERLAP)
     return invalid("unknown schedule");
   if (side_stream && (!fork_event || !join_event))

@@ -27,6 +27,7 @@ EXPORTED = [
     "ctr_step_unique", "ctr_embbag_bwd_sgd_sr", "ctr_sparse_sgd_sr", "ctr_sr_step_seed",
     "ctr_dot_interaction_self_fwd", "ctr_dot_interaction_self_bwd", "ctr_fm_interaction_fwd",
     "ctr_fm_interaction_bwd", "ctr_dict_build", "ctr_dict_lookup", "ctr_dict_embbag_fwd",
+    "ctr_dot_interaction_bwd_ex", "ctr_embbag_bwd_sgd_ex",
 ]
 
 CTR_STEP_POOLED_INTERACTION, CTR_STEP_BATCH_MATRIX = 0, 1
@@ -49,7 +50,7 @@ class CtrStep(ctypes.Structure):
                 ("ws_bwd_bytes", ctypes.c_size_t), ("uniq", _P * 2), ("inverse", _P * 2),
                 ("num_unique", _P * 2), ("perm", _P * 2), ("seg_offsets", _P * 2),
                 ("sorted_src", _P * 2), ("rounding", ctypes.c_int32),
-                ("sr_seed", ctypes.c_uint64)]
+                ("sr_seed", ctypes.c_uint64), ("grad_dtype", ctypes.c_int32)]
 
 _lib = None
 
@@ -95,6 +96,9 @@ def load() -> ctypes.CDLL:
         "ctr_dot_interaction_self_bwd": (i32, [P, P, i64, i64, i32, i32, i32, P, P]),
         "ctr_fm_interaction_fwd": (i32, [P, i64, i32, i32, P, P]),
         "ctr_fm_interaction_bwd": (i32, [P, P, i64, i32, i32, P, P]),
+        "ctr_dot_interaction_bwd_ex": (i32, [P, P, i64, i64, i32, i32, i32, i32, i32, P, P]),
+        "ctr_embbag_bwd_sgd_ex": (i32, [P, i32, i64, i64, P, i64, i32, i64, P, P, P, i32, i64,
+                                        i32, P, f32, i32, u64, P, P, PS, P]),
         "ctr_dict_build": (i32, [P, P, P, i64, P, i64, P, P]),
         "ctr_dict_lookup": (i32, [P, i64, P, i64, P, P]),
         "ctr_dict_embbag_fwd": (i32, [P, i64, P, i64, i32, P, i64, P, i64, i32, i32, P, i64,
@@ -258,12 +262,19 @@ def ctr_embbag_bwd(grad: torch.Tensor, grad_stride_b: int, grad_stride_t: int,
                    workspace: Optional[torch.Tensor] = None,
                    sorted_src: Optional[torch.Tensor] = None, nnz: Optional[int] = None,
                    stream=None, prepare: bool = False):
-    """Per-row gradient sums; the grouping comes from ``sorted_src`` or from (perm, inverse)."""
+    """Per-row gradient sums; the grouping comes from ``sorted_src`` or from (perm, inverse).
+    A bf16 ``grad`` (summed in fp32) needs ``sorted_src``."""
     if nnz is None:
         nnz = sorted_src.shape[0] if sorted_src is not None else perm.numel()
     dev = grad.device
     if row_grads is None:
         row_grads = torch.empty((max(nnz, 1), dim), dtype=torch.float32, device=dev)
+    if grad.dtype == torch.bfloat16:
+        if workspace is None:
+            workspace = _workspace(embbag_bwd_workspace_bytes(nnz, dim), dev)
+        return _bwd_ex(grad, grad_stride_b, grad_stride_t, offsets, batch, num_tables, nnz,
+                       sorted_src, num_unique, None, None, dim, 0.0, CTR_ROUND_NEAREST, 0,
+                       row_grads, workspace, stream, prepare)
     args = (_ptr(grad), grad_stride_b, grad_stride_t, _ptr(offsets), batch, num_tables, dim, nnz,
             _ptr(perm), _ptr(inverse), _ptr(sorted_src), _ptr(num_unique), _ptr(row_grads))
     if workspace is None:
@@ -284,6 +295,10 @@ def ctr_embbag_bwd_sgd(grad: torch.Tensor, grad_stride_b: int, grad_stride_t: in
     total_rows, dim = table.shape
     if workspace is None:
         workspace = _workspace(embbag_bwd_workspace_bytes(nnz, dim), grad.device)
+    if grad.dtype == torch.bfloat16:
+        return _bwd_ex(grad, grad_stride_b, grad_stride_t, offsets, batch, num_tables, nnz,
+                       sorted_src, num_unique, table, uniq, dim, lr, CTR_ROUND_NEAREST, 0,
+                       row_grads, workspace, stream, prepare)
     wsb = ctypes.c_size_t(workspace.numel())
     args = (_ptr(grad), grad_stride_b, grad_stride_t, _ptr(offsets), batch, num_tables, nnz,
             _ptr(sorted_src), _ptr(num_unique), _ptr(table), _dtype_code(table), total_rows, dim,
@@ -302,12 +317,29 @@ def ctr_embbag_bwd_sgd_sr(grad: torch.Tensor, grad_stride_b: int, grad_stride_t:
     total_rows, dim = table.shape
     if workspace is None:
         workspace = _workspace(embbag_bwd_workspace_bytes(nnz, dim), grad.device)
+    if grad.dtype == torch.bfloat16:
+        return _bwd_ex(grad, grad_stride_b, grad_stride_t, offsets, batch, num_tables, nnz,
+                       sorted_src, num_unique, table, uniq, dim, lr, CTR_ROUND_STOCHASTIC, seed,
+                       row_grads, workspace, stream, prepare)
     wsb = ctypes.c_size_t(workspace.numel())
     args = (_ptr(grad), grad_stride_b, grad_stride_t, _ptr(offsets), batch, num_tables, nnz,
             _ptr(sorted_src), _ptr(num_unique), _ptr(table), _dtype_code(table), total_rows, dim,
             _ptr(uniq), ctypes.c_float(lr), ctypes.c_uint64(seed & 0xFFFFFFFFFFFFFFFF),
             _ptr(row_grads), _ptr(workspace), ctypes.byref(wsb))
     return _run("ctr_embbag_bwd_sgd_sr", args, stream, prepare, row_grads)
+
+
+def _bwd_ex(grad, sb, st, offsets, batch, num_tables, nnz, sorted_src, num_unique, table, uniq,
+            dim, lr, rounding, seed, row_grads, workspace, stream, prepare):
+    """ctr_embbag_bwd_sgd_ex: gradient dtype from the tensor; table None = row sums only."""
+    total_rows = 0 if table is None else table.shape[0]
+    wsb = ctypes.c_size_t(workspace.numel())
+    args = (_ptr(grad), _dtype_code(grad), sb, st, _ptr(offsets), batch, num_tables, nnz,
+            _ptr(sorted_src), _ptr(num_unique), _ptr(table),
+            CTR_F32 if table is None else _dtype_code(table), total_rows, dim, _ptr(uniq),
+            ctypes.c_float(lr), rounding, ctypes.c_uint64(seed & 0xFFFFFFFFFFFFFFFF),
+            _ptr(row_grads), _ptr(workspace), ctypes.byref(wsb))
+    return _run("ctr_embbag_bwd_sgd_ex", args, stream, prepare, row_grads)
 
 
 def ctr_sparse_sgd_sr(table: torch.Tensor, uniq: torch.Tensor, num_unique: torch.Tensor,
@@ -349,9 +381,13 @@ def ctr_dot_interaction_fwd(Z: torch.Tensor, compute: int = CTR_F32,
 def ctr_dot_interaction_bwd(Z: torch.Tensor, dR: torch.Tensor, compute: int = CTR_F32,
                             dZ: Optional[torch.Tensor] = None, stream=None,
                             prepare: bool = False):
+    """dZ fp32, or bf16 when ``dZ`` is a bf16 tensor (compute must be CTR_BF16)."""
     B, F, d = Z.shape
     if dZ is None:
         dZ = torch.empty_like(Z)
+    if dZ.dtype == torch.bfloat16:
+        args = (_ptr(Z), _ptr(dR), dR.stride(0), B, F, d, compute, 0, CTR_BF16, _ptr(dZ))
+        return _run("ctr_dot_interaction_bwd_ex", args, stream, prepare, dZ)
     args = (_ptr(Z), _ptr(dR), dR.stride(0), B, F, d, compute, _ptr(dZ))
     return _run("ctr_dot_interaction_bwd", args, stream, prepare, dZ)
 

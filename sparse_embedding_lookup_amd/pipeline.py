@@ -73,7 +73,11 @@ class FrontEnd:
             self.Z[:, 0, :].copy_(_dev(w.dense, self.device))        # batch upload
             self.R = torch.empty((B, d + w.P), dtype=torch.float32, device=self.device)
             self.dR = _dev(w.grad_out, self.device)
-            self.dZ = torch.empty_like(self.Z)
+            # a bf16 interaction keeps its gradient in bf16 (the backward re-reads it per
+            # occurrence and sums in fp32)
+            self.dZ = torch.empty(self.Z.shape, device=self.device,
+                                  dtype=torch.bfloat16 if self.compute == ctr.CTR_BF16
+                                  else torch.float32)
         else:
             n = w.nnz
             self.E = torch.empty((max(n, 1), d), dtype=torch.float32, device=self.device)
@@ -391,6 +395,7 @@ class FrontEnd:
         d.sr_seed = self.sr_seed
         if w.interaction:
             d.Z, d.R, d.dR, d.dZ = P(self.Z), P(self.R), P(self.dR), P(self.dZ)
+            d.grad_dtype = ctr._dtype_code(self.dZ)
         else:
             d.E, d.out, d.dout = P(self.E), P(self.out), P(self.dout)
         d.row_grads = P(self.row_grads)

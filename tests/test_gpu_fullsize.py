@@ -31,6 +31,8 @@ def say(*a):
 
 def host(t):
     torch.cuda.synchronize()
+    if t.dtype == torch.bfloat16:               # numpy has no bfloat16: widen (exact)
+        t = t.float()
     return t.detach().cpu().numpy()
 
 

@@ -33,6 +33,8 @@ def dev(a):
 
 def host(t):
     torch.cuda.synchronize()
+    if t.dtype == torch.bfloat16:               # numpy has no bfloat16: widen (exact)
+        t = t.float()
     return t.detach().cpu().numpy()
 
 
