@@ -7,8 +7,8 @@
 // (u, bag) per sorted position first (a wave expands 64 bags by a shuffle binary search
 // over their ends; then one gather in sorted order).  Then a deterministic reduce-by-key
 // over the sorted sequence in fixed chunks, so that a row hit a million times costs the
-// same as a million rows hit once.  A workgroup owns a chunk of S*kPerSlot positions; each
-// G-lane slot (G lanes x 16 B per row) sums kPerSlot consecutive positions, with every
+// same as a million rows hit once.  A workgroup owns a chunk of S*KPS positions; each
+// G-lane slot (G lanes x 16 B per row) sums KPS consecutive positions, with every
 // gradient row and every table row it needs requested before it adds anything, and writes
 // the segments it completes straight out (row_grads and/or the SGD update); the pieces of
 // segments that cross slot edges are joined in LDS; pieces that cross the chunk edges go
@@ -23,7 +23,15 @@ namespace ctr {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kPerSlot = 8;      // positions summed by one slot (more slots, fewer registers)
+// Positions summed by one slot (KPS): fewer positions mean fewer live registers per slot and
+// more slots per chunk.  The depth sets the summation tree, so it depends only on what is
+// summed, never on where the sums go: with or without the update, the same gradients give
+// the same row sums bit for bit.  fp32 gradient rows (16 bytes per lane) run best at 4,
+// packed bf16 rows at 6 (measured on the Small, TensorNet, Criteo-shaped and Large
+// workloads).  The workspace is sized for the smallest depth.
+template <bool GB>
+constexpr int slot_depth() { return GB ? 6 : 4; }
+constexpr int kMinSlotDepth = 4;
 constexpr int64_t kFoldBlocks = 256;   // a level this small may finish the tree in place
 
 __global__ __launch_bounds__(kThreads) void bag_of_kernel(const int64_t* __restrict__ offsets,
@@ -68,6 +76,7 @@ __global__ __launch_bounds__(kThreads) void seg_src_kernel(const int32_t* __rest
 // point at, fp32 or bf16 (GB; widened exactly).  Offsets are in elements.
 template <bool GB>
 struct L0SourceT {
+  static constexpr bool kBf16 = GB;
   const int4* src;
   const void* grad;
   int64_t sb, st, batch, num_bags;
@@ -209,7 +218,7 @@ struct PendingRow {
   WVec<MODE> w;
 };
 
-// Sum the slot's kPerSlot sorted positions when one 16-byte vector per lane covers a row
+// Sum the slot's KPS sorted positions when one 16-byte vector per lane covers a row
 // (d <= 4G).  Each sorted position carries (u, bag, table row), so the slot issues every
 // memory access it needs in two dependent rounds: its entries, then all gradient rows
 // together with the table rows of the segments it completes (and of its last piece, which
@@ -217,14 +226,14 @@ struct PendingRow {
 // differs; a piece whose key equals the key just before the slot began earlier (sorted
 // keys), and one whose key equals the key just after continues later: those two go to LDS
 // for the join, every other piece is complete and is written out (and applied) here.
-template <int G, int MODE, typename Src>
+template <int G, int MODE, int KPS, typename Src>
 __device__ __forceinline__ void slot_prefetched(const Src& S, int64_t q0, int64_t q1,
                                                 int64_t n, int dim, int64_t capacity,
                                                 float* __restrict__ row_grads,
                                                 const SgdTarget& sgd, SegSmem<G, 1>& sm, int slot,
                                                 int lane, int32_t& fkey, int32_t& fcont,
                                                 int32_t& lkey, PendingRow<MODE>& pend) {
-  constexpr int kRegs = (kPerSlot + G - 1) / G;
+  constexpr int kRegs = (KPS + G - 1) / G;
   const int lane0 = (threadIdx.x & 63) & ~(G - 1);
   const int len = (int)(q1 - q0);
   const int c = lane * 4;
@@ -240,7 +249,7 @@ __device__ __forceinline__ void slot_prefetched(const Src& S, int64_t q0, int64_
     ekey[r] = -1;
     ebag[r] = 0;
     erow[r] = -1;
-    if (e < kPerSlot && e < len) {
+    if (e < KPS && e < len) {
       const int4 sr = S.src[q0 + e];
       ekey[r] = sr.x;
       ebag[r] = sr.y;
@@ -251,10 +260,10 @@ __device__ __forceinline__ void slot_prefetched(const Src& S, int64_t q0, int64_
   const int32_t ka = key_after<true>(S, q1, n);
 
   // all gradient rows of the slot
-  int32_t kk[kPerSlot];
-  typename Src::Raw rv[kPerSlot];
+  int32_t kk[KPS];
+  typename Src::Raw rv[KPS];
 #pragma unroll
-  for (int e = 0; e < kPerSlot; ++e) {
+  for (int e = 0; e < KPS; ++e) {
     kk[e] = __shfl(ekey[e / G], lane0 + (e % G), 64);
     uint32_t bag = (uint32_t)__shfl(ebag[e / G], lane0 + (e % G), 64);
     if ((int64_t)bag >= S.num_bags) bag = 0;
@@ -265,7 +274,7 @@ __device__ __forceinline__ void slot_prefetched(const Src& S, int64_t q0, int64_
 
   // table rows of the segments completed inside the slot, and of the last piece
   int64_t rk[kRegs];
-  WVec<MODE> w[kPerSlot];
+  WVec<MODE> w[KPS];
   if constexpr (MODE != 0) {
 #pragma unroll
     for (int r = 0; r < kRegs; ++r) {
@@ -276,7 +285,7 @@ __device__ __forceinline__ void slot_prefetched(const Src& S, int64_t q0, int64_
       const int32_t wrap = (r + 1 < kRegs) ? __shfl(ekey[r + 1 < kRegs ? r + 1 : r], lane0, 64)
                                            : -1;
       const int32_t nx = (e + 1 < len) ? ((lane + 1 < G) ? up : wrap) : ka;
-      const bool emit = e < kPerSlot && e < len && own != kb && nx != own && own >= 0 &&
+      const bool emit = e < KPS && e < len && own != kb && nx != own && own >= 0 &&
                         (int64_t)own < capacity;
       const bool last = e == len - 1 && own == ka && own != kb && own >= 0 &&
                         (int64_t)own < capacity;
@@ -284,7 +293,7 @@ __device__ __forceinline__ void slot_prefetched(const Src& S, int64_t q0, int64_
       rk[r] = ((emit || last) && key >= 0 && key < sgd.total_rows) ? key : -1;
     }
 #pragma unroll
-    for (int e = 0; e < kPerSlot; ++e) {
+    for (int e = 0; e < KPS; ++e) {
       const int64_t key = __shfl(rk[e / G], lane0 + (e % G), 64);
       w[e] = load_wvec<MODE>(sgd, key, c, key >= 0 && col_ok);
     }
@@ -292,7 +301,7 @@ __device__ __forceinline__ void slot_prefetched(const Src& S, int64_t q0, int64_
 
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
-  for (int e = 0; e < kPerSlot; ++e) {
+  for (int e = 0; e < KPS; ++e) {
     if (e < len) {
       const float4 x = Src::widen(rv[e]);
       acc.x += x.x;
@@ -300,7 +309,7 @@ __device__ __forceinline__ void slot_prefetched(const Src& S, int64_t q0, int64_
       acc.z += x.z;
       acc.w += x.w;
       const int32_t k = kk[e];
-      const int32_t nx = (e + 1 < len) ? kk[e + 1 < kPerSlot ? e + 1 : e] : ka;
+      const int32_t nx = (e + 1 < len) ? kk[e + 1 < KPS ? e + 1 : e] : ka;
       if (nx != k) {                           // the piece ends at e
         if (k == kb) {                         // ... and began before the slot
           fkey = k;
@@ -336,7 +345,7 @@ __device__ __forceinline__ void slot_prefetched(const Src& S, int64_t q0, int64_
 // One chunk of a reduce-by-key level.  L0: entries are sorted positions of the occurrences
 // (keys from src, rows gathered from grad); otherwise entries are carries (keys may be -1 =
 // empty).  The chunk's at most two carries go to out_keys / out_rows[2 * chunk + {0, 1}].
-template <bool L0, int G, int VPL, int MODE, typename Src>
+template <bool L0, int G, int VPL, int MODE, int KPS, typename Src>
 __device__ __forceinline__ void reduce_chunk(
     SegSmem<G, VPL>& sm, Src S, int64_t n, int64_t chunk_id, int dim, int64_t capacity,
     float* __restrict__ row_grads, const SgdTarget& sgd, int32_t* __restrict__ out_keys,
@@ -345,10 +354,10 @@ __device__ __forceinline__ void reduce_chunk(
   constexpr int kW = G * VPL * 4;              // floats per slot row in LDS
   const int lane = threadIdx.x & (G - 1);
   const int slot = threadIdx.x / G;
-  const int64_t chunk0 = chunk_id * kSlots * kPerSlot;
-  const int64_t q0 = chunk0 + (int64_t)slot * kPerSlot;
-  const int64_t q1 = q0 + kPerSlot < n ? q0 + kPerSlot : n;
-  const int64_t chunk1 = chunk0 + (int64_t)kSlots * kPerSlot < n ? chunk0 + (int64_t)kSlots * kPerSlot : n;
+  const int64_t chunk0 = chunk_id * kSlots * KPS;
+  const int64_t q0 = chunk0 + (int64_t)slot * KPS;
+  const int64_t q1 = q0 + KPS < n ? q0 + KPS : n;
+  const int64_t chunk1 = chunk0 + (int64_t)kSlots * KPS < n ? chunk0 + (int64_t)kSlots * KPS : n;
 
   // column of vector a of this lane
   auto col = [&](int a) { return (a * G + lane) * 4; };
@@ -391,12 +400,13 @@ __device__ __forceinline__ void reduce_chunk(
   PendingRow<MODE> pend;
   if constexpr (L0 && VPL == 1) {
     if (q0 < n)
-      slot_prefetched<G, MODE, Src>(S, q0, q1, n, dim, capacity, row_grads, sgd, sm, slot, lane,
+      slot_prefetched<G, MODE, KPS, Src>(S, q0, q1, n, dim, capacity, row_grads, sgd, sm, slot,
+                                         lane,
                                fkey, fcont, lkey, pend);
   } else if (q0 < n) {
     // Prefetch the slot's entries cooperatively: entry e is loaded by lane e % G of the slot
     // into register e / G, then broadcast with shuffles.
-    constexpr int kRegs = (kPerSlot + G - 1) / G;
+    constexpr int kRegs = (KPS + G - 1) / G;
     const int lane0 = (threadIdx.x & 63) & ~(G - 1);
     int32_t ekey[kRegs];
     int32_t ebag[kRegs];
@@ -406,7 +416,7 @@ __device__ __forceinline__ void reduce_chunk(
       const int64_t p = q0 + e;
       ekey[r] = -1;
       ebag[r] = 0;
-      if (e < kPerSlot && p < q1) {
+      if (e < KPS && p < q1) {
         if constexpr (L0) {
           const int4 sr = S.src[p];
           ekey[r] = sr.x;
@@ -423,9 +433,9 @@ __device__ __forceinline__ void reduce_chunk(
     bool first_seen = false;
     RowAcc<VPL> acc;
     acc.zero();
-    constexpr int kBatch = VPL == 1 ? kPerSlot : 8;
+    constexpr int kBatch = VPL == 1 ? KPS : (KPS < 8 ? KPS : 8);
 #pragma unroll
-    for (int b0 = 0; b0 < kPerSlot; b0 += kBatch) {
+    for (int b0 = 0; b0 < KPS; b0 += kBatch) {
       int32_t kk[kBatch];
       float4 rv[kBatch][VPL];
 #pragma unroll
@@ -589,7 +599,7 @@ __device__ __forceinline__ void reduce_chunk(
 // level (its writes published by a device-scope fence before the ticket; the finisher
 // fences again before it reads them), which saves a launch.  The L0 kernel, which always
 // precedes, zeroes the ticket.
-template <bool L0, int G, int VPL, int MODE, typename Src>
+template <bool L0, int G, int VPL, int MODE, int KPS, typename Src>
 __global__ __launch_bounds__(kThreads) void segreduce_kernel(
     Src S, int64_t n, int dim, int64_t capacity, float* __restrict__ row_grads, SgdTarget sgd,
     int32_t* __restrict__ out_keys, float* __restrict__ out_rows, uint32_t* __restrict__ ticket,
@@ -599,7 +609,7 @@ __global__ __launch_bounds__(kThreads) void segreduce_kernel(
   if constexpr (L0) {
     if (ticket && blockIdx.x == 0 && threadIdx.x == 0) *ticket = 0u;
   }
-  reduce_chunk<L0, G, VPL, MODE, Src>(sm, S, n, (int64_t)blockIdx.x, dim, capacity, row_grads,
+  reduce_chunk<L0, G, VPL, MODE, KPS, Src>(sm, S, n, (int64_t)blockIdx.x, dim, capacity, row_grads,
                                       sgd, out_keys, out_rows);
   if constexpr (!L0) {
     if (ticket) {
@@ -612,7 +622,7 @@ __global__ __launch_bounds__(kThreads) void segreduce_kernel(
       if (finisher) {
         __threadfence();
         const LnSource fin{out_keys, out_rows, dim};
-        reduce_chunk<false, G, VPL, MODE, LnSource>(sm, fin, 2 * (int64_t)gridDim.x, 0, dim,
+        reduce_chunk<false, G, VPL, MODE, KPS, LnSource>(sm, fin, 2 * (int64_t)gridDim.x, 0, dim,
                                                     capacity, row_grads, sgd, nullptr,
                                                     spare_rows);
       }
@@ -631,9 +641,9 @@ struct BwdWs {
   size_t bytes;
 };
 
-int64_t chunk_positions(int dim) {
+int64_t chunk_positions(int dim, int kps) {
   const RowGeom rg = row_geom(dim / 4);
-  return (int64_t)(kThreads / rg.G) * kPerSlot;
+  return (int64_t)(kThreads / rg.G) * kps;
 }
 
 BwdWs carve(void* base, int64_t n, int dim) {
@@ -645,7 +655,7 @@ BwdWs carve(void* base, int64_t n, int dim) {
     off += align256(sz);
     return p;
   };
-  const int64_t chunk = chunk_positions(dim);
+  const int64_t chunk = chunk_positions(dim, kMinSlotDepth);
   const int64_t c1 = 2 * ((n + chunk - 1) / chunk);   // carries out of level 0 (largest)
   w.bag_of = reinterpret_cast<int32_t*>(take(sizeof(int32_t) * (size_t)n));
   w.src = reinterpret_cast<int4*>(take(sizeof(int4) * (size_t)n));
@@ -684,12 +694,13 @@ template <int MODE, typename L0S>
 static void segreduce_levels(const L0S& s0, int64_t nnz, int dim, float* row_grads,
                              const SgdTarget& sgd, BwdWs& w, hipStream_t s) {
   const RowGeom rg = row_geom(dim / 4);
-  const int64_t chunk = chunk_positions(dim);
+  constexpr int KPS = slot_depth<L0S::kBf16>();
+  const int64_t chunk = chunk_positions(dim, KPS);
   CTR_SEG_DISPATCH(rg.G, rg.VPL, {
     int64_t len = nnz;
     int64_t blocks = (len + chunk - 1) / chunk;
     int cur = 0;
-    segreduce_kernel<true, G, VPL, MODE, L0S><<<(unsigned)blocks, kThreads, 0, s>>>(
+    segreduce_kernel<true, G, VPL, MODE, KPS, L0S><<<(unsigned)blocks, kThreads, 0, s>>>(
         s0, len, dim, nnz, row_grads, sgd, blocks > 1 ? w.ckeys[cur] : nullptr, w.crows[cur],
         w.ticket, nullptr);
     while (blocks > 1) {
@@ -698,7 +709,7 @@ static void segreduce_levels(const L0S& s0, int64_t nnz, int dim, float* row_gra
       LnSource sn{w.ckeys[cur], w.crows[cur], dim};
       // a level whose carries fit one chunk finishes the tree itself
       const bool fold = blocks > 1 && 2 * blocks <= chunk && blocks <= kFoldBlocks;
-      segreduce_kernel<false, G, VPL, MODE, LnSource><<<(unsigned)blocks, kThreads, 0, s>>>(
+      segreduce_kernel<false, G, VPL, MODE, KPS, LnSource><<<(unsigned)blocks, kThreads, 0, s>>>(
           sn, len, dim, nnz, row_grads, sgd, blocks > 1 ? w.ckeys[cur ^ 1] : nullptr,
           w.crows[cur ^ 1], fold ? w.ticket : nullptr, w.crows[cur]);
       cur ^= 1;
