@@ -436,8 +436,10 @@ def main():
                     help="pipelined: batch k+1's ID dedup runs during step k (double-buffered "
                          "outputs); serial: every step dedups its own batch first")
     ap.add_argument("--pipeline", default="overlap",
-                    choices=["overlap", "early", "after-pooling"],
-                    help="pipelined schedule of the native step: overlap (each step waits for "
+                    choices=["overlap2", "overlap", "early", "after-pooling"],
+                    help="pipelined schedule of the native step: overlap2 (two batches' "
+                         "uniques in flight on two side streams, three output sets), overlap "
+                         "(each step waits for "
                          "its batch's unique only before its backward; steps overlap), early "
                          "(the next batch's unique forked at the step start, joined at its "
                          "end) or after-pooling (forked after the pooling kernel)")
@@ -471,7 +473,8 @@ def main():
     native = args.launch in ("native", "graph")
     pipelined = args.schedule == "pipelined"
     sched = args.pipeline if pipelined else "serial"
-    if graph and pipelined and args.steps % 2:
+    deep = sched == "overlap2"
+    if graph and pipelined and not deep and args.steps % 2:
         args.steps += 1                  # a pipelined graph holds whole pairs of steps
     if args.rounding == "stochastic" and w.dtype != "bf16":
         print("--rounding stochastic needs a bf16-table workload (criteo, large)", file=sys.stderr)
@@ -495,7 +498,7 @@ def main():
     def warm():
         if native:
             if pipelined:
-                fe.native_start()
+                fe.native_start(deep=deep)
             for _ in range(args.warmup):
                 fe.step_native(sched)
         elif pipelined:
@@ -575,10 +578,10 @@ def main():
     if graph:
         g_steps = fe.capture_native(K, sched, [e for pair in zip(dev0, dev1) for e in pair])
         if pipelined:
-            fe.native_start()
+            fe.native_start(deep=deep)
         g_steps.replay()                 # warm replay
         if pipelined:
-            fe.native_start()            # set 0 for the first step (the unique of the step
+            fe.native_start(deep=deep)            # set 0 for the first step (the unique of the step
                                          # before; the graph's last step fills it again)
         torch.cuda.synchronize()
         t0 = time.perf_counter()
@@ -656,6 +659,9 @@ def main():
                       "(double-buffered outputs)%s; every call runs once per step"
                       % ({"overlap": "; each backward waits only for its own batch's dedup, "
                                      "so consecutive steps overlap",
+                          "overlap2": "; two batches' uniques in flight on two side "
+                                      "streams (three output sets), each backward waits only "
+                                      "for its own batch's",
                           "early": ", forked when the step starts, joined at its end",
                           "after-pooling": ", forked after the pooling kernel, joined at "
                                            "the step's end"}[args.pipeline] if native

@@ -378,13 +378,15 @@ int32_t ctr_validate_csr(const void* indices, int32_t index_type, int64_t nnz,
  *     -> ctr_embbag_bwd_sgd over dout (SGD on the touched table rows).
  *     E, out, dout: fp32 [nnz, dim].
  *
- * Unique outputs exist twice (index 0 and 1) for the pipelined schedule; the serial
- * schedule uses index 0 only (index 1 may repeat index 0).  Each array has capacity nnz
+ * Unique outputs exist in CTR_STEP_SETS = 3 sets: the serial schedule uses set 0, the
+ * pipelined schedules of ctr_step_run sets 0 and 1, ctr_step_run_deep all three (an unused
+ * set may repeat set 0).  Each array has capacity nnz
  * (seg_offsets nnz + 1; sorted_src 4 int32 per position, 16-byte aligned).  Workspaces are
  * sized by the two-call queries of ctr_unique_ids and ctr_embbag_bwd.  row_grads
  * (fp32 [nnz, dim]) is optional.
  */
 enum { CTR_STEP_POOLED_INTERACTION = 0, CTR_STEP_BATCH_MATRIX = 1 };
+#define CTR_STEP_SETS 3
 enum { CTR_ROUND_NEAREST = 0, CTR_ROUND_STOCHASTIC = 1 };
 enum {
   CTR_SCHEDULE_SERIAL = 0,
@@ -421,17 +423,19 @@ typedef struct {
   size_t ws_unique_bytes;
   void* ws_bwd;
   size_t ws_bwd_bytes;
-  int64_t* uniq[2];
-  int32_t* inverse[2];
-  int32_t* num_unique[2];
-  int32_t* perm[2];               /* nullable */
-  int32_t* seg_offsets[2];        /* nullable */
-  int32_t* sorted_src[2];
+  int64_t* uniq[CTR_STEP_SETS];
+  int32_t* inverse[CTR_STEP_SETS];
+  int32_t* num_unique[CTR_STEP_SETS];
+  int32_t* perm[CTR_STEP_SETS];               /* nullable */
+  int32_t* seg_offsets[CTR_STEP_SETS];        /* nullable */
+  int32_t* sorted_src[CTR_STEP_SETS];
   int32_t rounding;               /* CTR_ROUND_NEAREST, or CTR_ROUND_STOCHASTIC (bf16 table):
                                      step k updates with seed ctr_sr_step_seed(sr_seed, k) */
   uint64_t sr_seed;
   int32_t grad_dtype;             /* element type of dZ: CTR_F32, or CTR_BF16 (compute must be
                                      CTR_BF16; dZ then holds bf16 [batch, F, dim]) */
+  void* ws_unique2;               /* ctr_step_run_deep: the second side stream's unique */
+  size_t ws_unique2_bytes;        /*   workspace (two uniques run at once) */
 } ctr_step_t;
 
 /*
@@ -464,9 +468,28 @@ int32_t ctr_step_run(const ctr_step_t* step, int64_t k, int32_t schedule, void* 
                      void* side_stream, void* fork_event, void* join_event, void* mark_begin,
                      void* mark_end);
 
-/* ctr_step_unique -- the unique of the step's batch into set 0 or 1 on `stream` (primes
- * the pipelined schedule). */
+/* ctr_step_unique -- the unique of the step's batch into set 0, 1 or 2 on `stream` (primes
+ * the pipelined schedules). */
 int32_t ctr_step_unique(const ctr_step_t* step, int32_t set, void* stream);
+
+/*
+ * ctr_step_run_deep -- the overlapped schedule two batches deep.  Step k trains on set
+ * k % 3 and forks batch k+2's unique into set (k+2) % 3 on side_stream(k % 2), so that two
+ * uniques (each a chain of small, latency-bound kernels) are in flight beside the main
+ * chain.  Only what the data needs is ordered:
+ *   the backward of step k waits for the unique that filled set k % 3 (step k >= 2);
+ *   batch k+2's unique waits for the backward of step k-1, which read set (k+2) % 3.
+ * Before step 0, fill sets 0 and 1 with ctr_step_unique on main_stream (steps 0 and 1 wait
+ * on nothing earlier, so a captured run of steps depends on nothing outside it).  events:
+ * six caller-created events, carried between calls (record nothing else into them):
+ * events[0..2] = unique of set j done, events[3..5] = backward that read set j done.  Before
+ * reading results (or at the end of a capture) make main_stream wait for both side streams.
+ * mark_begin/mark_end as in ctr_step_run.  The uniques on side_stream0 use ws_unique, those
+ * on side_stream1 ws_unique2 (both sized by ctr_unique_ids' query).
+ */
+int32_t ctr_step_run_deep(const ctr_step_t* step, int64_t k, void* main_stream,
+                          void* side_stream0, void* side_stream1, void* const* events,
+                          void* mark_begin, void* mark_end);
 
 #ifdef __cplusplus
 }

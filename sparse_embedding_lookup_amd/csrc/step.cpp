@@ -58,17 +58,18 @@ int32_t wait(hipStream_t s, void* ev) {
     if (st_ != CTR_OK) return st_;  \
   } while (0)
 
-int32_t unique_into(const ctr_step_t* d, int set, void* stream) {
-  size_t wsb = d->ws_unique_bytes;
+// The batch's unique into output set `set`, with workspace 0 (ws_unique) or 1 (ws_unique2).
+int32_t unique_into(const ctr_step_t* d, int set, void* stream, int ws = 0) {
+  void* wsp = ws ? d->ws_unique2 : d->ws_unique;
+  size_t wsb = ws ? d->ws_unique2_bytes : d->ws_unique_bytes;
   if (d->kind == CTR_STEP_POOLED_INTERACTION)
     return ctr_unique_ids(d->indices, d->index_type, d->nnz, d->offsets, d->batch,
                           d->num_tables, d->row_base, d->total_rows, 0, d->uniq[set],
                           d->inverse[set], d->num_unique[set], d->perm[set], d->seg_offsets[set],
-                          d->sorted_src[set], d->ws_unique, &wsb, stream);
+                          d->sorted_src[set], wsp, &wsb, stream);
   return ctr_unique_ids(d->indices, d->index_type, d->nnz, nullptr, 0, 0, nullptr, 0,
                         d->key_modulus, d->uniq[set], d->inverse[set], d->num_unique[set],
-                        d->perm[set], d->seg_offsets[set], d->sorted_src[set], d->ws_unique, &wsb,
-                        stream);
+                        d->perm[set], d->seg_offsets[set], d->sorted_src[set], wsp, &wsb, stream);
 }
 
 // The stages before the unique may fork (pooling, and for the batch-matrix step the gather).
@@ -131,8 +132,44 @@ int32_t ctr_step_unique(const ctr_step_t* d, int32_t set, void* stream) {
   if (!d) return invalid("step is NULL");
   if (d->kind != CTR_STEP_POOLED_INTERACTION && d->kind != CTR_STEP_BATCH_MATRIX)
     return invalid("unknown step kind");
-  if (set < 0 || set > 1) return invalid("set must be 0 or 1");
+  if (set < 0 || set >= CTR_STEP_SETS) return invalid("set must be 0, 1 or 2");
   return unique_into(d, set, stream);
+}
+
+int32_t ctr_step_run_deep(const ctr_step_t* d, int64_t k, void* main_stream, void* side_stream0,
+                          void* side_stream1, void* const* events, void* mark_begin,
+                          void* mark_end) {
+  if (!d) return invalid("step is NULL");
+  if (d->kind != CTR_STEP_POOLED_INTERACTION && d->kind != CTR_STEP_BATCH_MATRIX)
+    return invalid("unknown step kind");
+  if (k < 0) return invalid("step index k < 0");
+  if (d->rounding != CTR_ROUND_NEAREST && d->rounding != CTR_ROUND_STOCHASTIC)
+    return invalid("unknown rounding");
+  if (d->grad_dtype != CTR_F32 && d->grad_dtype != CTR_BF16) return invalid("unknown grad_dtype");
+  if (!side_stream0 || !side_stream1 || !events) return invalid("two side streams and six events are required");
+  for (int i = 0; i < 6; ++i)
+    if (!events[i]) return invalid("two side streams and six events are required");
+  if (!d->ws_unique2) return invalid("the two-deep schedule needs the second unique workspace");
+  hipStream_t s = static_cast<hipStream_t>(main_stream);
+  hipStream_t side = static_cast<hipStream_t>((k & 1) ? side_stream1 : side_stream0);
+  void* const* udone = events;            // udone[j]: the unique that filled set j is done
+  void* const* bdone = events + 3;        // bdone[j]: the backward that read set j is done
+  const int cur = (int)(k % 3), ahead = (int)((k + 2) % 3);
+  // Batch k trains on set k % 3: filled by the unique forked in step k - 2, or, for the first
+  // two steps, by the caller on the main stream before step 0 (so that a captured sequence
+  // of steps waits on nothing recorded outside it).
+  CTR_TRY(forward_part(d, cur, s, mark_begin, mark_end));
+  CTR_TRY(interaction_part(d, s));
+  if (k >= 2) CTR_TRY(wait(s, udone[cur]));
+  // Batch k + 2's unique, on the side stream of its parity, into the set the backward of
+  // step k - 1 released (step 0: a set nothing has read; the record only forks the stream).
+  if (k == 0) CTR_TRY(record(bdone[ahead], s));
+  CTR_TRY(wait(side, bdone[ahead]));
+  // two uniques can run at once, one per side stream: each stream has its own workspace
+  CTR_TRY(unique_into(d, ahead, side, (int)(k & 1)));
+  CTR_TRY(record(udone[ahead], side));
+  CTR_TRY(sgd_part(d, cur, k, s));
+  return record(bdone[cur], s);
 }
 
 int32_t ctr_step_run(const ctr_step_t* d, int64_t k, int32_t schedule, void* main_stream,

@@ -27,7 +27,7 @@ EXPORTED = [
     "ctr_step_unique", "ctr_embbag_bwd_sgd_sr", "ctr_sparse_sgd_sr", "ctr_sr_step_seed",
     "ctr_dot_interaction_self_fwd", "ctr_dot_interaction_self_bwd", "ctr_fm_interaction_fwd",
     "ctr_fm_interaction_bwd", "ctr_dict_build", "ctr_dict_lookup", "ctr_dict_embbag_fwd",
-    "ctr_dot_interaction_bwd_ex", "ctr_embbag_bwd_sgd_ex",
+    "ctr_dot_interaction_bwd_ex", "ctr_embbag_bwd_sgd_ex", "ctr_step_run_deep",
 ]
 
 CTR_STEP_POOLED_INTERACTION, CTR_STEP_BATCH_MATRIX = 0, 1
@@ -47,10 +47,11 @@ class CtrStep(ctypes.Structure):
                 ("lr", ctypes.c_float), ("Z", _P), ("R", _P), ("dR", _P), ("dZ", _P), ("E", _P),
                 ("out", _P), ("dout", _P), ("row_grads", _P), ("ws_unique", _P),
                 ("ws_unique_bytes", ctypes.c_size_t), ("ws_bwd", _P),
-                ("ws_bwd_bytes", ctypes.c_size_t), ("uniq", _P * 2), ("inverse", _P * 2),
-                ("num_unique", _P * 2), ("perm", _P * 2), ("seg_offsets", _P * 2),
-                ("sorted_src", _P * 2), ("rounding", ctypes.c_int32),
-                ("sr_seed", ctypes.c_uint64), ("grad_dtype", ctypes.c_int32)]
+                ("ws_bwd_bytes", ctypes.c_size_t), ("uniq", _P * 3), ("inverse", _P * 3),
+                ("num_unique", _P * 3), ("perm", _P * 3), ("seg_offsets", _P * 3),
+                ("sorted_src", _P * 3), ("rounding", ctypes.c_int32),
+                ("sr_seed", ctypes.c_uint64), ("grad_dtype", ctypes.c_int32),
+                ("ws_unique2", _P), ("ws_unique2_bytes", ctypes.c_size_t)]
 
 _lib = None
 
@@ -109,6 +110,7 @@ def load() -> ctypes.CDLL:
         "ctr_validate_csr": (i32, [P, i32, i64, P, i64, i32, P, i64, P, P]),
         "ctr_step_run": (i32, [P, i64, i32, P, P, P, P, P, P]),
         "ctr_step_unique": (i32, [P, i32, P]),
+        "ctr_step_run_deep": (i32, [P, i64, P, P, P, P, P, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -474,6 +476,29 @@ def ctr_step_run(step: CtrStep, k: int, schedule: int, main_stream=None, side_st
                                  side_stream.cuda_stream),
                              ev(fork_event), ev(join_event), ev(mark_begin), ev(mark_end))
     _check("ctr_step_run", st)
+
+
+def ctr_step_run_deep(step: CtrStep, k: int, main_stream, side_streams, events,
+                      mark_begin=None, mark_end=None) -> None:
+    """Enqueue step k of the two-deep overlapped schedule; side_streams: two torch streams;
+    events: six torch.cuda.Event objects carried between calls."""
+    ms = main_stream if main_stream is not None else torch.cuda.current_stream()
+
+    def ev(e):
+        if e is None:
+            return None
+        if not e.cuda_event:
+            e.record(ms)                  # torch creates the HIP event on its first record
+        return e.cuda_event
+
+    arr = (ctypes.c_void_p * 6)(*[ev(e) for e in events])
+    st = load().ctr_step_run_deep(ctypes.byref(step), k, ctypes.c_void_p(ms.cuda_stream),
+                                  ctypes.c_void_p(side_streams[0].cuda_stream),
+                                  ctypes.c_void_p(side_streams[1].cuda_stream),
+                                  ctypes.cast(arr, ctypes.c_void_p),
+                                  None if mark_begin is None else ctypes.c_void_p(ev(mark_begin)),
+                                  None if mark_end is None else ctypes.c_void_p(ev(mark_end)))
+    _check("ctr_step_run_deep", st)
 
 
 def ctr_step_unique(step: CtrStep, set_index: int, stream=None) -> None:

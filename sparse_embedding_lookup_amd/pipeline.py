@@ -91,7 +91,7 @@ class FrontEnd:
                                      device=dv)
         self.ws_bwd = torch.empty(max(ctr.embbag_bwd_workspace_bytes(n, d), 256),
                                   dtype=torch.uint8, device=dv)
-        self._sets = [self._unique_buffers(n, dv) for _ in range(2 if pipelined else 1)]
+        self._sets = [self._unique_buffers(n, dv) for _ in range(3 if pipelined else 1)]
         self._calls = []
         self.side = None
         self._k = 0
@@ -400,8 +400,11 @@ class FrontEnd:
             d.E, d.out, d.dout = P(self.E), P(self.out), P(self.dout)
         d.row_grads = P(self.row_grads)
         d.ws_unique, d.ws_unique_bytes = P(self.ws_unique), self.ws_unique.numel()
+        if self.pipelined:            # the two-deep schedule runs two uniques at once
+            self.ws_unique2 = torch.empty_like(self.ws_unique)
+            d.ws_unique2, d.ws_unique2_bytes = P(self.ws_unique2), self.ws_unique2.numel()
         d.ws_bwd, d.ws_bwd_bytes = P(self.ws_bwd), self.ws_bwd.numel()
-        for i in range(2):
+        for i in range(3):
             b = self._sets[min(i, len(self._sets) - 1)]
             d.uniq[i], d.inverse[i] = P(b["uniq"]), P(b["inverse"])
             d.num_unique[i], d.perm[i] = P(b["num_unique"]), P(b["perm"])
@@ -412,56 +415,89 @@ class FrontEnd:
         self._ev_join.record()
         if self.side is None:
             self.side = torch.cuda.Stream(device=self.device)
+        # the two-deep schedule: a second side stream and six events carried between steps
+        self.side2 = torch.cuda.Stream(device=self.device)
+        self._ev_deep = [torch.cuda.Event() for _ in range(6)]
+        for e in self._ev_deep:
+            e.record()
         return d
 
-    def native_start(self):
-        """Prime the native pipelined schedule: the first batch's unique into set 0."""
-        ctr.ctr_step_unique(self.native(), 0)
+    def native_start(self, deep: bool = False):
+        """Prime the native pipelined schedules: the first batch's unique into set 0, and for
+        the two-deep schedule ("overlap2") the second batch's into set 1, on the current
+        stream."""
+        d = self.native()
+        ctr.ctr_step_unique(d, 0)
+        if deep:
+            ctr.ctr_step_unique(d, 1)
         self._k = 0
 
     SCHEDULES = {"serial": ctr.CTR_SCHEDULE_SERIAL,
                  "after-pooling": ctr.CTR_SCHEDULE_PIPELINED,
                  "early": ctr.CTR_SCHEDULE_PIPELINED_EARLY,
-                 "overlap": ctr.CTR_SCHEDULE_PIPELINED_OVERLAP}
+                 "overlap": ctr.CTR_SCHEDULE_PIPELINED_OVERLAP,
+                 "overlap2": None}                 # ctr_step_run_deep
+
+    def _run_native(self, k: int, schedule: str, stream, mark_begin=None, mark_end=None,
+                    side=None):
+        d = self.native()
+        if schedule == "overlap2":
+            ctr.ctr_step_run_deep(d, k, stream, [self.side, self.side2], self._ev_deep,
+                                  mark_begin, mark_end)
+        else:
+            ctr.ctr_step_run(d, k, self.SCHEDULES[schedule], stream,
+                             side if side is not None else self.side, self._ev_fork,
+                             self._ev_join, mark_begin, mark_end)
+
+    def _set_of(self, k: int, schedule: str) -> int:
+        if schedule == "serial":
+            return 0
+        return k % 3 if schedule == "overlap2" else k & 1
 
     def step_native(self, schedule: str = "serial", mark_begin=None, mark_end=None):
-        """One whole step in one native call (ctr_step_run) under `schedule` (a key of
-        SCHEDULES; the pipelined ones need FrontEnd(pipelined=True) and native_start() before
-        the first step); mark_begin/mark_end (optional torch.cuda.Event) bracket the pooling
-        kernel.  After it, the unique outputs of the step's batch are the attributes (set
-        k % 2 when pipelined).  With "overlap" the next batch's unique may still be running
-        on the side stream: native_join() (or a device synchronize) before reading it."""
-        code = self.SCHEDULES[schedule]
-        pipelined = code != ctr.CTR_SCHEDULE_SERIAL
-        assert self.pipelined or not pipelined, "the pipelined schedules need two buffer sets"
-        d = self.native()
+        """One whole step in one native call (ctr_step_run, or ctr_step_run_deep for
+        "overlap2") under `schedule` (a key of SCHEDULES; the pipelined ones need
+        FrontEnd(pipelined=True) and native_start() before the first step, native_start(
+        deep=True) for "overlap2"); mark_begin/mark_end (optional torch.cuda.Event) bracket
+        the pooling kernel.  After it, the unique outputs of the step's batch are the
+        attributes.  With the overlapped schedules the next batches' uniques may still be
+        running on the side streams: native_join() (or a device synchronize) before reading
+        them."""
+        pipelined = schedule != "serial"
+        assert self.pipelined or not pipelined, "the pipelined schedules need the buffer sets"
         k = self._k
-        ctr.ctr_step_run(d, k, code, torch.cuda.current_stream(self.device), self.side,
-                         self._ev_fork, self._ev_join, mark_begin, mark_end)
-        self._use_set((k & 1) if pipelined else 0)
+        self._run_native(k, schedule, torch.cuda.current_stream(self.device), mark_begin,
+                         mark_end)
+        self._use_set(self._set_of(k, schedule))
         self._k = k + 1
 
     def native_join(self):
-        """Make the current stream wait for the side stream (the overlapped unique)."""
-        torch.cuda.current_stream(self.device).wait_stream(self.side)
+        """Make the current stream wait for the side streams (the overlapped uniques)."""
+        cur = torch.cuda.current_stream(self.device)
+        cur.wait_stream(self.side)
+        if getattr(self, "side2", None) is not None:
+            cur.wait_stream(self.side2)
 
     def capture_native(self, steps: int, schedule: str = "serial", marks=None, side=None):
         """Record `steps` consecutive native steps (k = 0 .. steps-1; an even count for the
-        pipelined schedules, whose set 0 must be primed before each replay) into one HIP
-        graph, ending with a join of the side stream.  marks: optional list of 2*steps timing
-        events around each step's pooling kernel, left timed by every replay."""
-        code = self.SCHEDULES[schedule]
-        assert code == ctr.CTR_SCHEDULE_SERIAL or (self.pipelined and steps % 2 == 0)
-        d = self.native()
-        side = side if side is not None else self.side
+        one-deep pipelined schedules, whose set 0 must be primed before each replay; sets 0
+        and 1 for "overlap2") into one HIP graph, ending with a join of the side streams.
+        marks: optional list of 2*steps timing events around each step's pooling kernel, left
+        timed by every replay."""
+        assert schedule in self.SCHEDULES
+        assert schedule == "serial" or (self.pipelined and (schedule == "overlap2" or
+                                                            steps % 2 == 0))
+        self.native()
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
             cap = torch.cuda.current_stream(self.device)
             for i in range(steps):
                 m0 = marks[2 * i] if marks else None
                 m1 = marks[2 * i + 1] if marks else None
-                ctr.ctr_step_run(d, i, code, cap, side, self._ev_fork, self._ev_join, m0, m1)
-            cap.wait_stream(side)
+                self._run_native(i, schedule, cap, m0, m1, side)
+            cap.wait_stream(side if side is not None else self.side)
+            if schedule == "overlap2":
+                cap.wait_stream(self.side2)
         self._use_set(0)
         return g
 

@@ -257,5 +257,15 @@ def test_step_run_bad_args():
         ctr.CTR_ERR_INVALID_ARGUMENT
     assert lib.ctr_step_run(ctypes.byref(d), 0, 5, None, None, None, None, None, None) == \
         ctr.CTR_ERR_INVALID_ARGUMENT
-    assert lib.ctr_step_unique(ctypes.byref(d), 2, None) == ctr.CTR_ERR_INVALID_ARGUMENT
+    assert lib.ctr_step_unique(ctypes.byref(d), 3, None) == ctr.CTR_ERR_INVALID_ARGUMENT
+    # the two-deep schedule: two side streams, six events and a second unique workspace
+    ev6 = (ctypes.c_void_p * 6)(*([0x10000] * 6))
+    assert lib.ctr_step_run_deep(ctypes.byref(d), 0, None, FAKE, None, ctypes.cast(ev6, ctypes.c_void_p),
+                                 None, None) == ctr.CTR_ERR_INVALID_ARGUMENT
+    assert lib.ctr_step_run_deep(ctypes.byref(d), 0, None, FAKE, FAKE, None, None, None) == \
+        ctr.CTR_ERR_INVALID_ARGUMENT
+    assert lib.ctr_step_run_deep(ctypes.byref(d), 0, None, FAKE, FAKE,
+                                 ctypes.cast(ev6, ctypes.c_void_p), None, None) == \
+        ctr.CTR_ERR_INVALID_ARGUMENT
+    assert b"workspace" in lib.ctr_last_error()
 

@@ -605,7 +605,37 @@ def test_native_step_matches_python_steps(name, schedule):
         assert torch.equal(fa.table, fb.table)
 
 
-@pytest.mark.parametrize("schedule", ["serial", "early", "overlap"])
+@pytest.mark.parametrize("name", ["small_b256", "criteo_b128", "tensornet_b512"])
+def test_native_deep_schedule_matches_serial(name):
+    """ctr_step_run_deep (two batches' uniques in flight, three output sets) leaves the table,
+    the forward outputs and the row gradients bit-identical to serial steps, after every
+    step (with unrelated eager work and synchronizations in between)."""
+    w = {"small_b256": lambda: workloads.small(batch=256),
+         "criteo_b128": lambda: workloads.criteo(batch=128),
+         "tensornet_b512": lambda: workloads.tensornet(batch=512, slots=100,
+                                                       table_rows=500_000)}[name]()
+    say("native deep schedule", name)
+    fa = FrontEnd(w, DEV, keep_grads=True)
+    fb = FrontEnd(w, DEV, keep_grads=True, pipelined=True)
+    fb.native_start(deep=True)
+    junk = torch.randn(1 << 20, device=DEV)
+    for k in range(5):
+        fa.step()
+        fb.step_native("overlap2")
+        junk.mul_(1.0001).add_(1.0)
+        torch.cuda.synchronize()
+        U = int(host(fa.num_unique)[0])
+        assert U == int(host(fb.num_unique)[0])
+        np.testing.assert_array_equal(host(fa.uniq)[:U], host(fb.uniq)[:U])
+        np.testing.assert_array_equal(host(fa.row_grads)[:U], host(fb.row_grads)[:U])
+        if w.interaction:
+            np.testing.assert_array_equal(host(fa.R), host(fb.R))
+        else:
+            np.testing.assert_array_equal(host(fa.out), host(fb.out))
+        assert torch.equal(fa.table, fb.table), k
+
+
+@pytest.mark.parametrize("schedule", ["serial", "early", "overlap", "overlap2"])
 @pytest.mark.parametrize("name", ["small_b256", "tensornet_b512"])
 def test_native_step_graph_matches_eager(name, schedule):
     """Native steps captured as one HIP graph (the timing marks as event-record nodes) and
@@ -623,13 +653,14 @@ def test_native_step_graph_matches_eager(name, schedule):
     for m in marks:
         m.record()
     torch.cuda.synchronize()
+    deep = schedule == "overlap2"
     g = fb.capture_native(K, schedule, marks)
     if pipelined:
-        fa.native_start()
+        fa.native_start(deep=deep)
     junk = torch.randn(1 << 20, device=DEV)
     for _ in range(2):
         if pipelined:
-            fb.native_start()
+            fb.native_start(deep=deep)
         for _ in range(K):
             fa.step_native(schedule)
         g.replay()
