@@ -458,6 +458,131 @@ void orc_fm_bwd(const double* Z, const double* zmag, const double* dout, int64_t
   }
 }
 
+/* ------------------------------------------------------------------ dense layers, head */
+/* [DLRM] 02 "Arquitetura": the continuous features pass through a bottom MLP whose output is
+ * the dense vector of the interaction; the interaction's output passes through a top MLP
+ * and a sigmoid that gives the click probability.  One fully connected layer, written from
+ * its definition: Y[m][n] = act(b[n] + sum_k X[m][k] W[n][k]), act = ReLU (max(., 0)) or the
+ * identity.  X [M][K], W [N][K], b [N] or NULL, Y [M][N].  bf16: each product takes X and W
+ * rounded to bf16 nearest-even (the bias is added as it is).  Xm: magnitudes of X (NULL:
+ * |X|); Ym = |b| + sum |x| |w|. */
+void orc_dense_fwd(const double* X, const double* Xm, int64_t M, int32_t K, const double* W,
+                   const double* b, int32_t N, int32_t relu, int32_t bf16, double* Y,
+                   double* Ym) {
+#pragma omp parallel for schedule(static)
+  for (int64_t m = 0; m < M; ++m)
+    for (int64_t n = 0; n < N; ++n) {
+      double s = b ? b[n] : 0.0, a = b ? fabs(b[n]) : 0.0;
+      for (int64_t k = 0; k < K; ++k) {
+        double x = X[m * K + k], w = W[n * K + k];
+        if (bf16) {
+          x = orc_round_bf16(x);
+          w = orc_round_bf16(w);
+        }
+        s += x * w;
+        a += (Xm ? Xm[m * K + k] : fabs(x)) * fabs(w);
+      }
+      Y[m * N + n] = (relu && !(s > 0.0)) ? 0.0 : s;
+      Ym[m * N + n] = a;
+    }
+}
+
+/* The layer's backward and the SGD step of its parameters, by the chain rule on the
+ * definition above with the gradients summed over the M rows:
+ *   dA[m][n] = dY[m][n] if the layer is linear or Y[m][n] > 0, else 0
+ *   dX[m][k] = sum_n dA[m][n] W[n][k]
+ *   W'[n][k] = W[n][k] - lr sum_m dA[m][n] X[m][k]
+ *   b'[n]    = b[n] - lr sum_m dA[m][n]
+ * bf16: dA, W and X are rounded to bf16 nearest-even in the products (the bias sum is of the
+ * unrounded dA).  W' and b' are rounded once to binary32, the stored parameter type.
+ * Magnitudes: dXm = sum |dA| |W|, Wm = |W| + lr sum |dA| |X|, bm = |b| + lr sum |dA|.
+ * dX, b, bn may be NULL. */
+void orc_dense_bwd_sgd(const double* X, int64_t M, int32_t K, const double* W, const double* b,
+                       int32_t N, int32_t relu, const double* Y, const double* dY, int32_t bf16,
+                       double lr, double* dX, double* dXm, double* Wn, double* Wm, double* bn,
+                       double* bm) {
+  double* dA = (double*)malloc(sizeof(double) * (size_t)(M * N > 0 ? M * N : 1));
+  for (int64_t i = 0; i < M * N; ++i) dA[i] = (relu && !(Y[i] > 0.0)) ? 0.0 : dY[i];
+  if (dX) {
+#pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; ++m)
+      for (int64_t k = 0; k < K; ++k) {
+        double s = 0.0, a = 0.0;
+        for (int64_t n = 0; n < N; ++n) {
+          double g = dA[m * N + n], w = W[n * K + k];
+          if (bf16) {
+            g = orc_round_bf16(g);
+            w = orc_round_bf16(w);
+          }
+          s += g * w;
+          a += fabs(g) * fabs(w);
+        }
+        dX[m * K + k] = s;
+        dXm[m * K + k] = a;
+      }
+  }
+#pragma omp parallel for schedule(static)
+  for (int64_t n = 0; n < N; ++n) {
+    for (int64_t k = 0; k < K; ++k) {
+      double s = 0.0, a = 0.0;
+      for (int64_t m = 0; m < M; ++m) {
+        double g = dA[m * N + n], x = X[m * K + k];
+        if (bf16) {
+          g = orc_round_bf16(g);
+          x = orc_round_bf16(x);
+        }
+        s += g * x;
+        a += fabs(g) * fabs(x);
+      }
+      Wn[n * K + k] = orc_round_f32(W[n * K + k] - lr * s);
+      Wm[n * K + k] = fabs(W[n * K + k]) + lr * a;
+    }
+    if (b && bn) {
+      double s = 0.0, a = 0.0;
+      for (int64_t m = 0; m < M; ++m) {
+        s += dA[m * N + n];
+        a += fabs(dA[m * N + n]);
+      }
+      bn[n] = orc_round_f32(b[n] - lr * s);
+      bm[n] = fabs(b[n]) + lr * a;
+    }
+  }
+  free(dA);
+}
+
+/* The logistic head and normalized entropy.  [DLRM] 02: a sigmoid gives the click
+ * probability p = 1 / (1 + e^-s).  [DHEN] 7.1 "Setup": NE = (mean binary cross-entropy) /
+ * H(q), q the empirical click rate of the labels, H(q) = -(q ln q + (1-q) ln(1-q));
+ * Solution 17: the cross-entropy of a logit is softplus(s) - y s, here
+ * (max(s, 0) - y s) + log1p(e^-|s|).  Per element: prob, the gradient of the mean
+ * cross-entropy (p - y) / M and its magnitude (p + |y|) / M.  stats = [sum ce, sum y, NE]
+ * (NE is NaN when q is 0 or 1); stats_mag = [sum |terms of ce|, sum |y|, NE magnitude
+ * (sum |terms| / M / H(q))]. */
+void orc_logistic_ne(const double* s, const double* y, int64_t M, double* prob, double* dl,
+                     double* dlm, double* stats, double* stats_mag) {
+  double sce = 0.0, sy = 0.0, ace = 0.0, ay = 0.0;
+  for (int64_t i = 0; i < M; ++i) {
+    const double x = s[i], l = y[i];
+    const double p = 1.0 / (1.0 + exp(-x));
+    const double sp = log1p(exp(-fabs(x)));
+    sce += (fmax(x, 0.0) - l * x) + sp;
+    ace += fabs(fmax(x, 0.0)) + fabs(l * x) + sp;
+    sy += l;
+    ay += fabs(l);
+    prob[i] = p;
+    dl[i] = (p - l) / (double)M;
+    dlm[i] = (p + fabs(l)) / (double)M;
+  }
+  const double q = sy / (double)M;
+  const double h = -(q * log(q) + (1.0 - q) * log(1.0 - q));
+  stats[0] = sce;
+  stats[1] = sy;
+  stats[2] = (q > 0.0 && q < 1.0) ? (sce / (double)M) / h : NAN;
+  stats_mag[0] = ace;
+  stats_mag[1] = ay;
+  stats_mag[2] = (q > 0.0 && q < 1.0) ? (ace / (double)M) / h : NAN;
+}
+
 /* ------------------------------------------------------------------ exported dictionary */
 /* [TN] "Inference Optimization": online inference looks raw IDs up in a pre-exported sparse
  * embedding dictionary.  The dictionary is the list (keys[e], rows[e], hot[e]) of its n

@@ -61,6 +61,10 @@ def _load():
         "orc_interaction_self_bwd": (None, [P, P, P, i64, i32, i32, P, P]),
         "orc_fm_fwd": (None, [P, P, i64, i32, i32, P, P]),
         "orc_fm_bwd": (None, [P, P, P, i64, i32, i32, P, P]),
+        "orc_dense_fwd": (None, [P, P, i64, i32, P, P, i32, i32, i32, P, P]),
+        "orc_dense_bwd_sgd": (None, [P, i64, i32, P, P, i32, i32, P, P, i32, ctypes.c_double,
+                                     P, P, P, P, P, P]),
+        "orc_logistic_ne": (None, [P, P, i64, P, P, P, P, P]),
         "orc_dict_lookup": (None, [P, P, P, P, i64, P, i64, P]),
         "orc_dict_pool": (None, [P, u64, i64, i32, i32, P, P, i64, i32, P, P]),
         "orc_sr_bf16": (f64, [f64, ctypes.c_uint32]),
@@ -253,6 +257,57 @@ def fm_bwd(Z, dout, zmag=None):
     dm = np.empty_like(dZ)
     _load().orc_fm_bwd(_p(Z), _p(zm), _p(dout), B, F, d, _p(dZ), _p(dm))
     return dZ, dm
+
+
+# ------------------------------------------------------------------------ MLP layers, head
+def dense_fwd(X, W, b, relu: bool, bf16: bool, xmag=None):
+    """One layer Y = act(X W^T + b): returns (Y, Ym) [M, N] float64.  X [M, K], W [N, K],
+    b [N] or None."""
+    X = _c(X, np.float64)
+    W = _c(W, np.float64)
+    M, K = X.shape
+    N = W.shape[0]
+    assert W.shape[1] == K
+    bb = None if b is None else _c(b, np.float64)
+    xm = None if xmag is None else _c(xmag, np.float64)
+    Y = np.empty((M, N), dtype=np.float64)
+    Ym = np.empty_like(Y)
+    _load().orc_dense_fwd(_p(X), _p(xm), M, K, _p(W), _p(bb), N, int(bool(relu)),
+                          int(bool(bf16)), _p(Y), _p(Ym))
+    return Y, Ym
+
+
+def dense_bwd_sgd(X, W, b, relu: bool, Y, dY, bf16: bool, lr: float, want_dx: bool = True):
+    """The layer's backward and SGD step: returns a dict with dX, dXm [M, K] (if want_dx),
+    W, Wm [N, K] (updated, binary32 values) and b, bm [N] (if b is not None)."""
+    X = _c(X, np.float64)
+    W = _c(W, np.float64)
+    M, K = X.shape
+    N = W.shape[0]
+    dY = _c(dY, np.float64)
+    Yd = _c(Y if Y is not None else np.zeros((M, N)), np.float64)
+    bb = None if b is None else _c(b, np.float64)
+    out = {"W": np.empty((N, K)), "Wm": np.empty((N, K))}
+    if want_dx:
+        out["dX"], out["dXm"] = np.empty((M, K)), np.empty((M, K))
+    if bb is not None:
+        out["b"], out["bm"] = np.empty(N), np.empty(N)
+    _load().orc_dense_bwd_sgd(_p(X), M, K, _p(W), _p(bb), N, int(bool(relu)), _p(Yd), _p(dY),
+                              int(bool(bf16)), float(lr), _p(out.get("dX")), _p(out.get("dXm")),
+                              _p(out["W"]), _p(out["Wm"]), _p(out.get("b")), _p(out.get("bm")))
+    return out
+
+
+def logistic_ne(s, y):
+    """Logistic head: returns (prob, dlogits, dlogits_mag) [M] and (stats, stats_mag) [3],
+    stats = [sum ce, sum y, NE]."""
+    s = _c(s, np.float64).ravel()
+    y = _c(y, np.float64).ravel()
+    M = s.size
+    prob, dl, dlm = np.empty(M), np.empty(M), np.empty(M)
+    st, stm = np.empty(3), np.empty(3)
+    _load().orc_logistic_ne(_p(s), _p(y), M, _p(prob), _p(dl), _p(dlm), _p(st), _p(stm))
+    return prob, dl, dlm, st, stm
 
 
 # ------------------------------------------------------------------------ a8, a9
