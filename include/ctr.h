@@ -491,6 +491,60 @@ int32_t ctr_step_run_deep(const ctr_step_t* step, int64_t k, void* main_stream,
                           void* side_stream0, void* side_stream1, void* const* events,
                           void* mark_begin, void* mark_end);
 
+/*
+ * ---------------------------------------------------------------- dense layers and head
+ * The layers on either side of the interaction ([DLRM] 02 "Arquitetura": the continuous
+ * features pass through a bottom MLP whose output is the dense vector z_0; the interaction
+ * output R passes through a top MLP and a sigmoid that gives the click probability; 05: the
+ * public ads data has 13 continuous features, the bottom MLP's input width) and the loss
+ * ([DHEN] 7.1 "Setup": normalized entropy; Solution 17: the stable cross-entropy form).
+ *
+ * ctr_dense_fwd -- one fully connected layer on the matrix cores:
+ *   Y[m, n] = act(sum_k X[m, k] W[n, k] + b[n]),  m < M, n < N, k < K,
+ * act = max(., 0) if relu else the identity.  X: fp32 rows of stride x_stride (>= K);
+ * W: fp32 [N, K] contiguous; b: fp32 [N] or NULL (no bias); Y: fp32 rows of stride y_stride
+ * (>= N; e.g. Z[:, 0, :] of the interaction input with y_stride = F * dim).
+ * compute: CTR_F32 (fp32 products and sums) or CTR_BF16 (X and W rounded to bf16
+ * nearest-even, fp32 accumulation).  1 <= K, N <= 65536.  M = 0 is a no-op.
+ */
+int32_t ctr_dense_fwd(const float* X, int64_t x_stride, int64_t M, int32_t K, const float* W,
+                      const float* b, int32_t N, int32_t relu, int32_t compute, float* Y,
+                      int64_t y_stride, void* stream);
+
+/*
+ * ctr_dense_bwd_sgd -- the layer's backward with the SGD update of its parameters fused.
+ * Given dY = dL/dY (fp32, or bf16 with dy_dtype = CTR_BF16; rows of stride dy_stride):
+ *   dA = dY * [Y > 0] if relu (Y: the forward's output) else dY
+ *   dX = dA W          (written only if dX != NULL; uses W before the update)
+ *   W  = W - lr * dA^T X,   b = b - lr * sum_m dA[m, :]   (b may be NULL)
+ * Gradients are sums over the M rows.  With compute = CTR_BF16 the GEMM operands (dA, W, X)
+ * are rounded to bf16 nearest-even and accumulate in fp32; the bias gradient sums fp32 dA.
+ * The weight-gradient reduction may be split over the rows into partials summed in a fixed
+ * order: results are deterministic.  workspace: two-call query (size grows with M * N and,
+ * for few output tiles, with N * K).  M = 0 is a no-op (W and b unchanged).
+ */
+int32_t ctr_dense_bwd_sgd(const float* X, int64_t x_stride, int64_t M, int32_t K, float* W,
+                          float* b, int32_t N, int32_t relu, const float* Y, int64_t y_stride,
+                          const void* dY, int32_t dy_dtype, int64_t dy_stride, int32_t compute,
+                          float lr, float* dX, int64_t dx_stride, void* workspace,
+                          size_t* workspace_bytes, void* stream);
+
+/*
+ * ctr_logistic_ne -- the logistic head over M >= 1 logits s[i] = logits[i * logit_stride]
+ * with labels y[i] (fp32, 0 or 1; values in between are taken as given):
+ *   prob[i]    = sigmoid(s[i])                          (if prob != NULL)
+ *   dlogits[i * dl_stride] = (prob[i] - y[i]) / M        (if dlogits != NULL: the gradient
+ *                                                         of the mean cross-entropy)
+ *   stats[0] = sum_i ce_i,  ce_i = softplus(s_i) - y_i s_i   (the cross-entropy in nats)
+ *   stats[1] = sum_i y_i
+ *   stats[2] = NE = (stats[0] / M) / H(q),  q = stats[1] / M,
+ *              H(q) = -(q ln q + (1 - q) ln(1 - q)); NaN if q is 0 or 1.
+ * stats: device fp32 [3].  One block: M is a batch.
+ */
+int32_t ctr_logistic_ne(const float* logits, int64_t logit_stride, const float* labels,
+                        int64_t M, float* prob, float* dlogits, int64_t dl_stride, float* stats,
+                        void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -573,6 +573,82 @@ int32_t ctr_init_table_hash(void* table, int32_t dtype, int32_t dim, const int64
   return CTR_OK;
 }
 
+// ---------------------------------------------------------------- dense layers and head
+constexpr int32_t kMaxWidth = 65536;       // layer widths (inputs K, outputs N)
+
+static int32_t check_dense(int64_t M, int32_t K, int32_t N, int32_t compute, int64_t x_stride,
+                           int64_t y_stride) {
+  if (M < 0 || M > kMaxElems) return fail(CTR_ERR_INVALID_ARGUMENT, "bad batch rows M");
+  if (K < 1 || K > kMaxWidth || N < 1 || N > kMaxWidth)
+    return fail(CTR_ERR_INVALID_ARGUMENT, "layer widths must be in [1, %d] (got K=%d, N=%d)",
+                kMaxWidth, K, N);
+  if (compute != CTR_F32 && compute != CTR_BF16)
+    return fail(CTR_ERR_INVALID_ARGUMENT, "compute %d is not CTR_F32 or CTR_BF16", compute);
+  if (x_stride < K) return fail(CTR_ERR_INVALID_ARGUMENT, "x_stride < K");
+  if (y_stride < N) return fail(CTR_ERR_INVALID_ARGUMENT, "y_stride < N");
+  if (M * (int64_t)N > kMaxElems * 64 || M * (int64_t)K > kMaxElems * 64)
+    return fail(CTR_ERR_INVALID_ARGUMENT, "M * N and M * K must be below 2^37");
+  return CTR_OK;
+}
+
+int32_t ctr_dense_fwd(const float* X, int64_t x_stride, int64_t M, int32_t K, const float* W,
+                      const float* b, int32_t N, int32_t relu, int32_t compute, float* Y,
+                      int64_t y_stride, void* stream) {
+  g_msg[0] = 0;
+  int32_t st = check_dense(M, K, N, compute, x_stride, y_stride);
+  if (st) return st;
+  if (M > 0 && (!X || !W || !Y)) return fail(CTR_ERR_INVALID_ARGUMENT, "X, W and Y are required");
+  return hip_status(ctr::launch_dense_fwd(X, x_stride, M, K, W, b, N, relu != 0,
+                                          compute == CTR_BF16, Y, y_stride,
+                                          (hipStream_t)stream),
+                    "ctr_dense_fwd");
+}
+
+int32_t ctr_dense_bwd_sgd(const float* X, int64_t x_stride, int64_t M, int32_t K, float* W,
+                          float* b, int32_t N, int32_t relu, const float* Y, int64_t y_stride,
+                          const void* dY, int32_t dy_dtype, int64_t dy_stride, int32_t compute,
+                          float lr, float* dX, int64_t dx_stride, void* workspace,
+                          size_t* workspace_bytes, void* stream) {
+  g_msg[0] = 0;
+  int32_t st = check_dense(M, K, N, compute, x_stride, y_stride);
+  if (st) return st;
+  if (dy_dtype != CTR_F32 && dy_dtype != CTR_BF16)
+    return fail(CTR_ERR_INVALID_ARGUMENT, "dy_dtype %d is not CTR_F32 or CTR_BF16", dy_dtype);
+  if (dy_stride < N) return fail(CTR_ERR_INVALID_ARGUMENT, "dy_stride < N");
+  if (dX && dx_stride < K) return fail(CTR_ERR_INVALID_ARGUMENT, "dx_stride < K");
+  if (!workspace_bytes) return fail(CTR_ERR_INVALID_ARGUMENT, "workspace_bytes is required");
+  const size_t need = ctr::dense_bwd_workspace_bytes(M, N, K);
+  if (!workspace) {
+    *workspace_bytes = need;
+    return CTR_OK;
+  }
+  if (*workspace_bytes < need)
+    return fail(CTR_ERR_WORKSPACE_TOO_SMALL, "workspace needs %zu bytes (got %zu)", need,
+                *workspace_bytes);
+  if (!aligned16(workspace)) return fail(CTR_ERR_UNSUPPORTED, "workspace is not 16-byte aligned");
+  if (M > 0 && (!X || !W || !dY || (relu && !Y)))
+    return fail(CTR_ERR_INVALID_ARGUMENT, "X, W, dY (and Y with relu) are required");
+  return hip_status(ctr::launch_dense_bwd_sgd(X, x_stride, M, K, W, b, N, relu != 0, Y, y_stride,
+                                              dY, dy_dtype == CTR_BF16, dy_stride,
+                                              compute == CTR_BF16, lr, dX, dx_stride, workspace,
+                                              (hipStream_t)stream),
+                    "ctr_dense_bwd_sgd");
+}
+
+int32_t ctr_logistic_ne(const float* logits, int64_t logit_stride, const float* labels,
+                        int64_t M, float* prob, float* dlogits, int64_t dl_stride, float* stats,
+                        void* stream) {
+  g_msg[0] = 0;
+  if (M < 1 || M > kMaxElems) return fail(CTR_ERR_INVALID_ARGUMENT, "bad M (need >= 1)");
+  if (logit_stride < 1 || (dlogits && dl_stride < 1))
+    return fail(CTR_ERR_INVALID_ARGUMENT, "strides must be >= 1");
+  if (!logits || !labels || !stats)
+    return fail(CTR_ERR_INVALID_ARGUMENT, "logits, labels and stats are required");
+  return hip_status(ctr::launch_logistic_ne(logits, logit_stride, labels, M, prob, dlogits,
+                                            dl_stride, stats, (hipStream_t)stream),
+                    "ctr_logistic_ne");
+}
+
 int32_t ctr_validate_csr(const void* indices, int32_t index_type, int64_t nnz,
                          const int64_t* offsets, int64_t batch, int32_t num_tables,
                          const int64_t* row_base, int64_t total_rows, int32_t* bad_count,

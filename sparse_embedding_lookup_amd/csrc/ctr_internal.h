@@ -173,4 +173,18 @@ hipError_t launch_fm_fwd(const float* Z, int64_t batch, int F, int dim, float* o
 hipError_t launch_fm_bwd(const float* Z, const float* dout, int64_t batch, int F, int dim,
                          float* dZ, hipStream_t s);
 
+// dense.hip: fully connected layers and the logistic head
+int dense_wgrad_splits(int64_t M, int N, int K, int64_t* k_split);
+size_t dense_bwd_workspace_bytes(int64_t M, int N, int K);
+hipError_t launch_dense_fwd(const float* X, int64_t xs, int64_t M, int K, const float* W,
+                            const float* b, int N, bool relu, bool bf16, float* Y, int64_t ys,
+                            hipStream_t s);
+hipError_t launch_dense_bwd_sgd(const float* X, int64_t xs, int64_t M, int K, float* W,
+                                float* b, int N, bool relu, const float* Y, int64_t ys,
+                                const void* dY, bool dy_bf16, int64_t dys, bool bf16, float lr,
+                                float* dX, int64_t dxs, void* workspace, hipStream_t s);
+hipError_t launch_logistic_ne(const float* logits, int64_t ls, const float* labels, int64_t M,
+                              float* prob, float* dlogits, int64_t dls, float* stats,
+                              hipStream_t s);
+
 }  // namespace ctr

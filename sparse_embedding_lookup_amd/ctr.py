@@ -28,6 +28,7 @@ EXPORTED = [
     "ctr_dot_interaction_self_fwd", "ctr_dot_interaction_self_bwd", "ctr_fm_interaction_fwd",
     "ctr_fm_interaction_bwd", "ctr_dict_build", "ctr_dict_lookup", "ctr_dict_embbag_fwd",
     "ctr_dot_interaction_bwd_ex", "ctr_embbag_bwd_sgd_ex", "ctr_step_run_deep",
+    "ctr_dense_fwd", "ctr_dense_bwd_sgd", "ctr_logistic_ne",
 ]
 
 CTR_STEP_POOLED_INTERACTION, CTR_STEP_BATCH_MATRIX = 0, 1
@@ -111,6 +112,10 @@ def load() -> ctypes.CDLL:
         "ctr_step_run": (i32, [P, i64, i32, P, P, P, P, P, P]),
         "ctr_step_unique": (i32, [P, i32, P]),
         "ctr_step_run_deep": (i32, [P, i64, P, P, P, P, P, P]),
+        "ctr_dense_fwd": (i32, [P, i64, i64, i32, P, P, i32, i32, i32, P, i64, P]),
+        "ctr_dense_bwd_sgd": (i32, [P, i64, i64, i32, P, P, i32, i32, P, i64, P, i32, i64, i32,
+                                    f32, P, i64, P, PS, P]),
+        "ctr_logistic_ne": (i32, [P, i64, P, i64, P, P, i64, P, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -434,6 +439,75 @@ def ctr_fm_interaction_bwd(Z: torch.Tensor, dout: torch.Tensor,
         dZ = torch.empty_like(Z)
     args = (_ptr(Z), _ptr(dout), B, F, d, _ptr(dZ))
     return _run("ctr_fm_interaction_bwd", args, stream, prepare, dZ)
+
+
+def _rows(t: torch.Tensor, name: str):
+    """(rows, width, row stride) of a 2-D fp32 view whose rows may be strided."""
+    if t.dim() != 2 or t.stride(1) != 1:
+        raise ValueError("%s must be 2-D with contiguous rows" % name)
+    return t.shape[0], t.shape[1], t.stride(0)
+
+
+def dense_bwd_workspace_bytes(M: int, K: int, N: int) -> int:
+    """Workspace of ctr_dense_bwd_sgd for M rows of a K -> N layer (the two-call query)."""
+    wsb = ctypes.c_size_t(0)
+    _check("ctr_dense_bwd_sgd", load().ctr_dense_bwd_sgd(None, K, M, K, None, None, N, 0, None,
+                                                         N, None, CTR_F32, N, CTR_F32, 0.0,
+                                                         None, K, None, ctypes.byref(wsb),
+                                                         None))
+    return wsb.value
+
+
+def ctr_dense_fwd(X: torch.Tensor, W: torch.Tensor, b: Optional[torch.Tensor], relu: bool,
+                  compute: int = CTR_F32, Y: Optional[torch.Tensor] = None, stream=None,
+                  prepare: bool = False):
+    """Y = act(X W^T + b) with X [M, K] (rows may be strided), W [N, K], b [N] or None; Y
+    [M, N] (rows may be strided, e.g. Z[:, 0, :])."""
+    M, K, xs = _rows(X, "X")
+    N = W.shape[0]
+    assert W.shape == (N, K) and W.is_contiguous()
+    if Y is None:
+        Y = torch.empty((M, N), dtype=torch.float32, device=X.device)
+    My, Ny, ys = _rows(Y, "Y")
+    assert (My, Ny) == (M, N)
+    args = (_ptr(X), xs, M, K, _ptr(W), _ptr(b), N, int(bool(relu)), compute, _ptr(Y), ys)
+    return _run("ctr_dense_fwd", args, stream, prepare, Y)
+
+
+def ctr_dense_bwd_sgd(X: torch.Tensor, W: torch.Tensor, b: Optional[torch.Tensor], relu: bool,
+                      Y: Optional[torch.Tensor], dY: torch.Tensor, lr: float,
+                      compute: int = CTR_F32, dX: Optional[torch.Tensor] = None,
+                      workspace: Optional[torch.Tensor] = None, stream=None,
+                      prepare: bool = False):
+    """The layer's backward with the SGD step of W and b in place; dX (if given) receives
+    dL/dX.  dY: fp32 or bf16 rows (may be strided)."""
+    M, K, xs = _rows(X, "X")
+    N = W.shape[0]
+    _, _, dys = _rows(dY, "dY")
+    ys = _rows(Y, "Y")[2] if Y is not None else N
+    dxs = _rows(dX, "dX")[2] if dX is not None else K
+    if workspace is None:
+        workspace = _workspace(dense_bwd_workspace_bytes(M, K, N), X.device)
+    wsb = ctypes.c_size_t(workspace.numel())
+    args = (_ptr(X), xs, M, K, _ptr(W), _ptr(b), N, int(bool(relu)), _ptr(Y), ys, _ptr(dY),
+            _dtype_code(dY), dys, compute, float(lr), _ptr(dX), dxs, _ptr(workspace),
+            ctypes.byref(wsb))
+    return _run("ctr_dense_bwd_sgd", args, stream, prepare, dX)
+
+
+def ctr_logistic_ne(logits: torch.Tensor, labels: torch.Tensor,
+                    prob: Optional[torch.Tensor] = None, dlogits: Optional[torch.Tensor] = None,
+                    stats: Optional[torch.Tensor] = None, stream=None, prepare: bool = False):
+    """Sigmoid, cross-entropy sums and NE of logits [M] (or [M, 1] with any row stride);
+    returns stats [3] = [sum ce, sum y, NE] (device).  dlogits, if given, receives the
+    gradient of the mean cross-entropy, shaped like logits."""
+    M = labels.numel()
+    ls = logits.stride(0)
+    dls = dlogits.stride(0) if dlogits is not None else 1
+    if stats is None:
+        stats = torch.empty(3, dtype=torch.float32, device=logits.device)
+    args = (_ptr(logits), ls, _ptr(labels), M, _ptr(prob), _ptr(dlogits), dls, _ptr(stats))
+    return _run("ctr_logistic_ne", args, stream, prepare, stats)
 
 
 def ctr_init_table_hash(table: torch.Tensor, rows: Sequence[int], seed: int, stream=None) -> None:

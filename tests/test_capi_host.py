@@ -269,3 +269,53 @@ def test_step_run_bad_args():
         ctr.CTR_ERR_INVALID_ARGUMENT
     assert b"workspace" in lib.ctr_last_error()
 
+
+
+def test_dense_and_head_bad_args():
+    lib = _lib()
+    fwd = dict(X=FAKE, xs=13, M=10, K=13, W=FAKE, b=None, N=4, relu=1, c=0, Y=FAKE, ys=4)
+
+    def f(**kw):
+        a = dict(fwd, **kw)
+        return lib.ctr_dense_fwd(a["X"], a["xs"], a["M"], a["K"], a["W"], a["b"], a["N"],
+                                 a["relu"], a["c"], a["Y"], a["ys"], None)
+
+    assert f(K=0) == ctr.CTR_ERR_INVALID_ARGUMENT
+    assert f(N=70000) == ctr.CTR_ERR_INVALID_ARGUMENT
+    assert f(c=7) == ctr.CTR_ERR_INVALID_ARGUMENT
+    assert f(xs=12) == ctr.CTR_ERR_INVALID_ARGUMENT
+    assert f(ys=3) == ctr.CTR_ERR_INVALID_ARGUMENT
+    assert f(W=None) == ctr.CTR_ERR_INVALID_ARGUMENT
+    assert f(M=-1) == ctr.CTR_ERR_INVALID_ARGUMENT
+    # backward: workspace query, then a too-small and a misaligned workspace
+    wsb = ctypes.c_size_t(0)
+    assert lib.ctr_dense_bwd_sgd(None, 13, 10, 13, None, None, 4, 1, None, 4, None, 0, 4, 0,
+                                 0.1, None, 13, None, ctypes.byref(wsb), None) == ctr.CTR_OK
+    assert wsb.value >= 10 * 4 * 4
+    assert wsb.value == ctr.dense_bwd_workspace_bytes(10, 13, 4)
+
+    def bw(ws, size, **kw):
+        a = dict(dt=0, dys=4, relu=1, Y=FAKE, dX=None, dxs=13)
+        a.update(kw)
+        s = ctypes.c_size_t(size)
+        return lib.ctr_dense_bwd_sgd(FAKE, 13, 10, 13, FAKE, None, 4, a["relu"], a["Y"], 4, FAKE,
+                                     a["dt"], a["dys"], 0, 0.1, a["dX"], a["dxs"], ws,
+                                     ctypes.byref(s), None)
+
+    assert bw(FAKE, 16) == ctr.CTR_ERR_WORKSPACE_TOO_SMALL
+    assert bw(MISALIGNED, wsb.value) == ctr.CTR_ERR_UNSUPPORTED
+    assert bw(FAKE, wsb.value, dt=3) == ctr.CTR_ERR_INVALID_ARGUMENT
+    assert bw(FAKE, wsb.value, dys=2) == ctr.CTR_ERR_INVALID_ARGUMENT
+    assert bw(FAKE, wsb.value, dX=FAKE, dxs=5) == ctr.CTR_ERR_INVALID_ARGUMENT
+    assert bw(FAKE, wsb.value, Y=None) == ctr.CTR_ERR_INVALID_ARGUMENT     # ReLU needs Y
+    assert lib.ctr_dense_bwd_sgd(FAKE, 13, 10, 13, FAKE, None, 4, 1, FAKE, 4, FAKE, 0, 4, 0, 0.1,
+                                 None, 13, FAKE, None, None) == ctr.CTR_ERR_INVALID_ARGUMENT
+    # head
+    assert lib.ctr_logistic_ne(FAKE, 1, FAKE, 0, None, None, 1, FAKE, None) == \
+        ctr.CTR_ERR_INVALID_ARGUMENT
+    assert lib.ctr_logistic_ne(FAKE, 1, None, 5, None, None, 1, FAKE, None) == \
+        ctr.CTR_ERR_INVALID_ARGUMENT
+    assert lib.ctr_logistic_ne(FAKE, 0, FAKE, 5, None, None, 1, FAKE, None) == \
+        ctr.CTR_ERR_INVALID_ARGUMENT
+    assert lib.ctr_logistic_ne(FAKE, 1, FAKE, 5, None, None, 1, None, None) == \
+        ctr.CTR_ERR_INVALID_ARGUMENT

@@ -1,0 +1,182 @@
+"""Fully connected layers, their backward with the SGD step, and the logistic head on the GPU
+through the C ABI, against the oracle ("Meta DLRM", 02: bottom and top MLP, sigmoid;
+"DHEN" notes, 7.1: normalized entropy).
+
+Per call on identical inputs, both sides round the same fp32 operands to bf16 (nearest-even)
+when the compute type is bf16, so the only difference left is the fp32 summation order: every
+check uses rtol = 1e-5 against the oracle's sum of |terms|, for both compute types.  Shapes
+span one and several 128x128 output tiles, ragged tails in every dimension, widths that are
+not multiples of 4 (scalar loads), strided rows, a one-unit output, and the split
+weight-gradient reduction.
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import oracle as orc
+from sparse_embedding_lookup_amd import ctr
+from tests.parity import RTOL_F32, assert_close
+from tests.test_gpu_parity import DEV, dev, host, say
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
+
+F32, BF16 = ctr.CTR_F32, ctr.CTR_BF16
+
+# (M, K, N, relu, bias, compute, x_pad, y_pad): x_pad / y_pad widen the row strides
+FWD_CASES = [
+    (1, 13, 512, True, True, F32, 0, 0),
+    (77, 13, 512, True, True, BF16, 0, 0),
+    (300, 479, 1024, True, True, F32, 0, 0),
+    (4099, 256, 128, True, False, BF16, 0, 0),
+    (129, 1024, 1, False, False, F32, 0, 0),
+    (64, 100, 33, False, True, F32, 28, 7),
+    (64, 100, 33, True, True, BF16, 28, 7),
+    (513, 64, 64, True, True, F32, 0, 8 * 64 - 64),     # Y = Z[:, 0, :] of a [513, 8, 64] Z
+    (200, 2208, 300, True, True, BF16, 0, 0),
+]
+
+
+def _layer(rng, M, K, N, scale_x=1.0):
+    X = (rng.standard_normal((M, K)) * scale_x).astype(np.float32)
+    W = rng.uniform(-1, 1, (N, K)).astype(np.float32) / np.float32(np.sqrt(K))
+    b = rng.uniform(-0.5, 0.5, N).astype(np.float32)
+    return X, W, b
+
+
+def _strided(a, pad):
+    """A device view of a with rows `pad` elements wider than needed."""
+    M, K = a.shape
+    big = torch.full((M, K + pad), float("nan"), device=DEV)
+    big[:, :K] = dev(a)
+    return big[:, :K]
+
+
+@pytest.mark.parametrize("M,K,N,relu,bias,compute,xp,yp", FWD_CASES)
+def test_dense_fwd_matches_oracle(M, K, N, relu, bias, compute, xp, yp):
+    say("dense_fwd", M, K, N, relu, bias, compute, xp, yp)
+    rng = np.random.default_rng(M + K + N)
+    X, W, b = _layer(rng, M, K, N)
+    Xd = _strided(X, xp)
+    big = torch.full((M, N + yp), -3.0, device=DEV)
+    Y = big[:, :N]
+    ctr.ctr_dense_fwd(Xd, dev(W), dev(b) if bias else None, relu, compute, Y)
+    want, mag = orc.dense_fwd(X, W, b if bias else None, relu, compute == BF16)
+    assert_close(host(Y), want, mag, RTOL_F32, "dense fwd")
+    if yp:
+        assert np.all(host(big)[:, N:] == -3.0)          # the padding is not written
+
+
+# (M, K, N, relu, bias, compute, with_dx, dy_bf16): the last three split the weight gradient
+BWD_CASES = [
+    (77, 13, 512, True, True, F32, False, False),
+    (300, 479, 256, True, True, BF16, True, False),
+    (129, 256, 1, False, True, F32, True, False),
+    (64, 100, 33, True, False, F32, True, False),
+    (513, 64, 64, True, True, BF16, True, True),
+    (64, 2048, 2048, True, True, F32, True, False),
+    (4096, 64, 64, True, True, F32, True, False),
+    (1024, 479, 256, True, True, BF16, True, False),
+    (3000, 13, 512, True, True, F32, False, False),
+]
+
+
+@pytest.mark.parametrize("M,K,N,relu,bias,compute,with_dx,dyb", BWD_CASES)
+def test_dense_bwd_sgd_matches_oracle(M, K, N, relu, bias, compute, with_dx, dyb):
+    say("dense_bwd_sgd", M, K, N, relu, bias, compute, with_dx, dyb)
+    rng = np.random.default_rng(1000 + M + K + N)
+    X, W, b = _layer(rng, M, K, N)
+    Wd, bd = dev(W), dev(b) if bias else None
+    Y = ctr.ctr_dense_fwd(dev(X), Wd, bd, relu, compute)
+    Yh = host(Y)
+    dY = rng.standard_normal((M, N)).astype(np.float32)
+    if dyb:                                   # a bf16 gradient: both sides see its values
+        dYd = dev(dY).to(torch.bfloat16)
+        dY = host(dYd).astype(np.float32)
+    else:
+        dYd = dev(dY)
+    dX = torch.full((M, K), float("nan"), device=DEV) if with_dx else None
+    lr = 0.01
+    ctr.ctr_dense_bwd_sgd(dev(X), Wd, bd, relu, Y, dYd, lr, compute, dX)
+    o = orc.dense_bwd_sgd(X, W, b if bias else None, relu, Yh, dY, compute == BF16, np.float32(lr),
+                          want_dx=with_dx)
+    assert_close(host(Wd), o["W"], o["Wm"], RTOL_F32, "W after the step")
+    if bias:
+        assert_close(host(bd), o["b"], o["bm"], RTOL_F32, "b after the step")
+    if with_dx:
+        assert_close(host(dX), o["dX"], o["dXm"], RTOL_F32, "dX")
+    if relu:
+        assert (Yh <= 0).any() and (Yh > 0).any()    # both sides of the mask are exercised
+
+
+def test_dense_bwd_deterministic_and_lr_zero():
+    rng = np.random.default_rng(7)
+    M, K, N = 4096, 64, 64                    # split weight gradient
+    X, W, b = _layer(rng, M, K, N)
+    dY = dev(rng.standard_normal((M, N)).astype(np.float32))
+    outs = []
+    for _ in range(2):
+        Wd, bd = dev(W), dev(b)
+        Y = ctr.ctr_dense_fwd(dev(X), Wd, bd, True, F32)
+        dX = torch.empty((M, K), device=DEV)
+        ctr.ctr_dense_bwd_sgd(dev(X), Wd, bd, True, Y, dY, 0.05, F32, dX)
+        outs.append((host(Wd), host(bd), host(dX)))
+    for a, c in zip(outs[0], outs[1]):
+        np.testing.assert_array_equal(a, c)
+    Wd, bd = dev(W), dev(b)
+    Y = ctr.ctr_dense_fwd(dev(X), Wd, bd, True, F32)
+    ctr.ctr_dense_bwd_sgd(dev(X), Wd, bd, True, Y, dY, 0.0, F32)
+    np.testing.assert_array_equal(host(Wd), W)
+    np.testing.assert_array_equal(host(bd), b)
+
+
+def test_dense_zero_rows_are_a_noop():
+    W = torch.ones((4, 3), device=DEV)
+    b = torch.zeros(4, device=DEV)
+    X = torch.empty((0, 3), device=DEV)
+    Y = ctr.ctr_dense_fwd(X, W, b, True)
+    assert Y.shape == (0, 4)
+    ctr.ctr_dense_bwd_sgd(X, W, b, True, Y, torch.empty((0, 4), device=DEV), 0.1)
+    torch.cuda.synchronize()
+    assert torch.all(W == 1) and torch.all(b == 0)
+
+
+@pytest.mark.parametrize("M,scale,stride", [(1, 1.0, 1), (1000, 3.0, 1), (8192, 2.0, 2),
+                                            (40000, 1.0, 1), (300, 80.0, 1)])
+def test_logistic_ne_matches_oracle(M, scale, stride):
+    say("logistic_ne", M, scale, stride)
+    rng = np.random.default_rng(M)
+    s = (rng.standard_normal(M) * scale).astype(np.float32)
+    y = (rng.random(M) < 0.3).astype(np.float32)
+    if M == 1:
+        y[0] = 1.0
+    big = torch.full((M, stride), float("nan"), device=DEV)
+    big[:, 0] = dev(s)
+    logits = big[:, 0]
+    prob = torch.empty(M, device=DEV)
+    dbig = torch.full((M, stride), -5.0, device=DEV)
+    dl = dbig[:, 0]
+    stats = ctr.ctr_logistic_ne(logits, dev(y), prob, dl)
+    p, g, gm, st, stm = orc.logistic_ne(s, y)
+    # 1e-30 / M: an absolute floor below which fp32 underflows (logits beyond about -87)
+    assert_close(host(prob), p, p + 1e-30, RTOL_F32, "prob")
+    assert_close(host(dl), g, gm + 1e-30 / M, RTOL_F32, "dlogits")
+    if stride > 1:
+        assert np.all(host(dbig)[:, 1:] == -5.0)
+    got = host(stats).astype(np.float64)
+    assert_close(got[:2], st[:2], stm[:2], RTOL_F32, "ce and label sums")
+    assert got[1] == y.sum()
+    if np.isnan(st[2]):
+        assert np.isnan(got[2])
+    else:
+        assert_close(got[2:], st[2:], stm[2:], RTOL_F32, "NE")
+
+
+def test_logistic_base_rate_gives_ne_one():
+    # every logit at the batch's click rate: NE = 1 ("DHEN" notes, Solution 16)
+    M = 5000
+    y = np.zeros(M, np.float32)
+    y[:1500] = 1
+    s = np.full(M, np.log(0.3 / 0.7), np.float32)
+    st = host(ctr.ctr_logistic_ne(dev(s), dev(y)))
+    assert abs(st[2] - 1.0) < 1e-5
