@@ -335,3 +335,45 @@ BUILDERS = {"tiny": tiny, "small": small, "criteo": criteo, "tensornet": tensorn
 
 def make(name: str, **kw) -> Workload:
     return BUILDERS[name](**kw)
+
+
+# ----------------------------------------------------------------------------- DLRM step
+DLRM_BOTTOM = (512, 256)            # hidden widths of the bottom MLP (output: the dim)
+DLRM_TOP = (1024, 1024, 512, 256)   # hidden widths of the top MLP (output: one logit)
+DLRM_DENSE = 13                     # continuous features per sample
+DLRM_CLICK_RATE = 0.25
+
+
+@dataclasses.dataclass
+class DlrmInputs:
+    """Inputs of a whole DLRM training step beside the sparse batch: continuous features,
+    click labels, and the initial MLP parameters (W [out, in], b [out]) per layer."""
+
+    dense_raw: np.ndarray           # fp32 [B, n_dense]
+    labels: np.ndarray              # fp32 [B], 0 or 1
+    bottom: List[tuple]             # [(W, b)], widths n_dense -> ... -> dim
+    top: List[tuple]                # [(W, b)], widths dim + P -> ... -> 1
+
+
+def dlrm_inputs(w: Workload, seed: int = 0, n_dense: int = DLRM_DENSE,
+                bottom=DLRM_BOTTOM, top=DLRM_TOP,
+                click_rate: float = DLRM_CLICK_RATE) -> DlrmInputs:
+    """Continuous features log-normal(0, 1), labels Bernoulli(click_rate), every weight and
+    bias U(-1/sqrt(fan_in), 1/sqrt(fan_in)); draws in that order, layers bottom to top."""
+    assert w.interaction
+    rng = np.random.default_rng(seed + 77)
+    B = w.batch
+    raw = rng.lognormal(0.0, 1.0, size=(B, n_dense)).astype(np.float32)
+    labels = (rng.random(B) < click_rate).astype(np.float32)
+
+    def mlp(widths):
+        layers = []
+        for fi, fo in zip(widths[:-1], widths[1:]):
+            a = np.float32(1.0 / math.sqrt(fi))
+            W = (rng.uniform(-1.0, 1.0, size=(fo, fi)).astype(np.float32) * a)
+            b = (rng.uniform(-1.0, 1.0, size=fo).astype(np.float32) * a)
+            layers.append((W, b))
+        return layers
+
+    return DlrmInputs(raw, labels, mlp([n_dense, *bottom, w.dim]),
+                      mlp([w.dim + w.P, *top, 1]))
