@@ -493,8 +493,9 @@ void orc_dense_fwd(const double* X, const double* Xm, int64_t M, int32_t K, cons
  *   dX[m][k] = sum_n dA[m][n] W[n][k]
  *   W'[n][k] = W[n][k] - lr sum_m dA[m][n] X[m][k]
  *   b'[n]    = b[n] - lr sum_m dA[m][n]
- * bf16: dA, W and X are rounded to bf16 nearest-even in the products (the bias sum is of the
- * unrounded dA).  W' and b' are rounded once to binary32, the stored parameter type.
+ * bf16: dA, W and X are rounded to bf16 nearest-even in the products; the bias is the weight
+ * of a constant input 1, so its sum takes the same rounded dA.  W' and b' are rounded once to
+ * binary32, the stored parameter type.
  * Magnitudes: dXm = sum |dA| |W|, Wm = |W| + lr sum |dA| |X|, bm = |b| + lr sum |dA|.
  * dX, b, bn may be NULL. */
 void orc_dense_bwd_sgd(const double* X, int64_t M, int32_t K, const double* W, const double* b,
@@ -540,8 +541,9 @@ void orc_dense_bwd_sgd(const double* X, int64_t M, int32_t K, const double* W, c
     if (b && bn) {
       double s = 0.0, a = 0.0;
       for (int64_t m = 0; m < M; ++m) {
-        s += dA[m * N + n];
-        a += fabs(dA[m * N + n]);
+        const double g = bf16 ? orc_round_bf16(dA[m * N + n]) : dA[m * N + n];
+        s += g;
+        a += fabs(g);
       }
       bn[n] = orc_round_f32(b[n] - lr * s);
       bm[n] = fabs(b[n]) + lr * a;

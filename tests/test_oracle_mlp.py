@@ -214,3 +214,23 @@ def test_two_layers_and_head_chain():
     # lr = 0 leaves every parameter as it was
     np.testing.assert_array_equal(g1["W"], W1)
     np.testing.assert_array_equal(g1["b"], b1)
+
+
+def test_dense_bf16_bias_step_is_the_ones_column():
+    """With bf16 operands the bias moves like the weight of an extra input fixed at 1: the
+    same step as a bias-free layer whose input has a column of ones appended."""
+    rng = np.random.default_rng(8)
+    M, K, N = 40, 6, 3
+    X = rng.standard_normal((M, K)).astype(np.float32)
+    W = rng.standard_normal((N, K)).astype(np.float32)
+    b = rng.standard_normal(N).astype(np.float32)
+    G = rng.standard_normal((M, N)).astype(np.float32)
+    o = orc.dense_bwd_sgd(X, W, b, False, None, G, True, 0.5)
+    Xa = np.concatenate([X, np.ones((M, 1), np.float32)], axis=1)
+    Wa = np.concatenate([W, b[:, None]], axis=1)
+    oa = orc.dense_bwd_sgd(Xa, Wa, None, False, None, G, True, 0.5)
+    np.testing.assert_array_equal(o["W"], oa["W"][:, :K])
+    np.testing.assert_array_equal(o["b"], oa["W"][:, K])
+    # and the rounding is there: the fp32-operand step differs
+    o32 = orc.dense_bwd_sgd(X, W, b, False, None, G, False, 0.5)
+    assert not np.array_equal(o["b"], o32["b"])
