@@ -196,6 +196,74 @@ def time_variants(fe, w, K: int):
     return res
 
 
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}   # MI355X dense matrix-core peaks
+
+
+def time_dlrm(fe, w, K: int):
+    """The whole DLRM training step around the front end (bottom MLP into Z[:, 0, :], top MLP,
+    logistic/NE head, backward with SGD of every parameter), sharing the front end's table:
+    K steps captured as one HIP graph and replayed; the dense part alone likewise; and each
+    layer's forward and backward call alone, priced against the matrix
+    cores' dense peak for the compute type (flops: 2 per multiply-add; forward B K N,
+    backward dX and dW 2 B K N, B K N for the first bottom layer, which has no dX).  Times
+    are K calls replayed from one HIP graph, divided by K."""
+    import torch
+    from sparse_embedding_lookup_amd import ctr, workloads
+    from sparse_embedding_lookup_amd.dlrm import DlrmStep
+
+    inp = workloads.dlrm_inputs(w)
+    s = DlrmStep(w, inp, "cuda", table=fe.table)
+    kind = "bf16" if s.compute == ctr.CTR_BF16 else "f32"
+    peak = MFMA_PEAK_TFLOPS[kind]
+    for _ in range(3):
+        s.step()
+    torch.cuda.synchronize()
+
+    def graph_ms(fn):
+        g = s.capture(steps=K, fn=fn)
+        g.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        g.replay()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) * 1e3 / K
+
+    step_ms = graph_ms(s.step)
+    mlp_ms = graph_ms(s.mlp_only)
+    B = w.batch
+    layers = []
+    calls = ([("bottom%d" % i, L, f, b, i == 0) for i, (L, f, b) in
+              enumerate(zip(s.bottom, s._fwd_bottom, s._bwd_bottom))] +
+             [("top%d" % i, L, f, b, False) for i, (L, f, b) in
+              enumerate(zip(s.top, s._fwd_top, s._bwd_top))])
+    for name, L, fwd, bwd, first in calls:
+        row = {"K": L.K, "N": L.N}
+        for part, call, mats in (("fwd", fwd, 1), ("bwd", bwd, 1 if first else 2)):
+            # K back-to-back calls replayed from a graph: launch gaps do not count
+            ms = graph_ms(call)
+            tf = 2.0 * B * L.K * L.N * mats / (ms * 1e-3) / 1e12
+            row[part + "_ms"] = round(ms, 5)
+            row[part + "_tflops"] = round(tf, 1)
+            row[part + "_frac"] = round(tf / peak, 4)
+        layers.append((name, row))
+    flops = s.mlp_flops()
+    big = max(layers, key=lambda kv: kv[1]["K"] * kv[1]["N"])
+    return {
+        "mlp": {"bottom": [13, *workloads.DLRM_BOTTOM, w.dim],
+                "top": [w.dim + w.P, *workloads.DLRM_TOP, 1], "compute": kind},
+        "step_ms": round(step_ms, 5),
+        "rows_per_s": w.nnz / (step_ms * 1e-3),
+        "samples_per_s": B / (step_ms * 1e-3),
+        "mlp_ms": round(mlp_ms, 5),
+        "mlp_tflops": round(flops / (mlp_ms * 1e-3) / 1e12, 1),
+        "ne": float(s.stats[2].item()),
+        "layers": dict(layers),
+        "roofline": {"kernel": big[0] + " backward (dX and dW GEMMs)", "bound": "mfma",
+                     "achieved": big[1]["bwd_tflops"], "peak": peak, "unit": "TFLOP/s",
+                     "frac": big[1]["bwd_frac"]},
+    }
+
+
 def measured_traffic(config: str, stage: str):
     """HBM bytes per launch of the stage's kernel from the committed rocprofv3 counter runs
     (FETCH_SIZE + WRITE_SIZE, each scaled by a plain copy of known size), or None when
@@ -449,6 +517,9 @@ def main():
     ap.add_argument("--no-variants", dest="variants", action="store_false",
                     help="skip timing the interaction variants (self-dots, FM sum) on the "
                          "workload's Z")
+    ap.add_argument("--no-dlrm", dest="dlrm", action="store_false",
+                    help="skip timing the whole DLRM step (bottom and top MLP, logistic/NE "
+                         "head) around the front end; it runs after the timed steps")
     ap.add_argument("--compare-serial", action="store_true",
                     help="after a pipelined run, also time K serial steps (ms_per_step_serial)")
     args = ap.parse_args()
@@ -635,6 +706,10 @@ def main():
         ms_serial = (time.perf_counter() - t2) * 1e3 / K
 
     variants = time_variants(fe, w, K) if (w.interaction and args.variants) else None
+    dlrm = None
+    if w.interaction and args.dlrm:
+        print("[bench] timing the whole DLRM step", file=sys.stderr, flush=True)
+        dlrm = time_dlrm(fe, w, K)
 
     step_bytes = sum(byts.values())
     value = w.nnz / (ms_step * 1e-3)
@@ -682,6 +757,7 @@ def main():
         "stage_ms_cold": ({k: round(v, 5) for k, v in stage_ms_cold.items()}
                           if stage_ms_cold else None),
         "variants": variants,
+        "dlrm": dlrm,
         "roofline": {"kernel": dominant, "bound": "hbm", "achieved": achieved,
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
                      "traffic": measured_traffic(

@@ -518,10 +518,12 @@ int32_t ctr_dense_fwd(const float* X, int64_t x_stride, int64_t M, int32_t K, co
  *   dX = dA W          (written only if dX != NULL; uses W before the update)
  *   W  = W - lr * dA^T X,   b = b - lr * sum_m dA[m, :]   (b may be NULL)
  * Gradients are sums over the M rows.  With compute = CTR_BF16 the GEMM operands (dA, W, X)
- * are rounded to bf16 nearest-even and accumulate in fp32; the bias gradient sums fp32 dA.
- * The weight-gradient reduction may be split over the rows into partials summed in a fixed
- * order: results are deterministic.  workspace: two-call query (size grows with M * N and,
- * for few output tiles, with N * K).  M = 0 is a no-op (W and b unchanged).
+ * are rounded to bf16 nearest-even and accumulate in fp32; the bias is the weight of a
+ * constant input 1, so its gradient is the same product (rounded dA times 1).  dA is never
+ * stored: it is formed from dY and Y as the GEMMs load it.  The weight-gradient reduction
+ * may be split over the rows into partials summed in a fixed order: results are
+ * deterministic.  workspace: two-call query (the partials, S * N * (K + 1) floats when the
+ * reduction is split; a small constant otherwise).  M = 0 is a no-op (W and b unchanged).
  */
 int32_t ctr_dense_bwd_sgd(const float* X, int64_t x_stride, int64_t M, int32_t K, float* W,
                           float* b, int32_t N, int32_t relu, const float* Y, int64_t y_stride,

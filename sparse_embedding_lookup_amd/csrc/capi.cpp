@@ -617,7 +617,8 @@ int32_t ctr_dense_bwd_sgd(const float* X, int64_t x_stride, int64_t M, int32_t K
   if (dy_stride < N) return fail(CTR_ERR_INVALID_ARGUMENT, "dy_stride < N");
   if (dX && dx_stride < K) return fail(CTR_ERR_INVALID_ARGUMENT, "dx_stride < K");
   if (!workspace_bytes) return fail(CTR_ERR_INVALID_ARGUMENT, "workspace_bytes is required");
-  const size_t need = ctr::dense_bwd_workspace_bytes(M, N, K);
+  const size_t need = ctr::dense_bwd_workspace_bytes(M, N, K, b != nullptr, relu != 0,
+                                                     compute == CTR_BF16);
   if (!workspace) {
     *workspace_bytes = need;
     return CTR_OK;

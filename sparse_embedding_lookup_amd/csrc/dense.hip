@@ -15,12 +15,16 @@
 //   dA = dY * [Y > 0] (ReLU) or dY;   dX = dA W (with W before the update);
 //   W -= lr dA^T X;                   b -= lr sum_m dA[m, :].
 // Gradients are sums over the batch rows (no 1/M), as for the embedding rows; the head's
-// gradient carries the 1/M of the mean cross-entropy.
+// gradient carries the 1/M of the mean cross-entropy.  The backward is one elementwise
+// pass and two GEMMs: dA (ReLU layers only) is written once in the GEMMs' operand type (bf16
+// nearest-even for bf16 compute, the rounding the GEMMs apply anyway, so half the bytes),
+// and the bias is the weight of a constant input 1, so its gradient is one more output
+// column of the weight-gradient GEMM (the input X read with a column of ones appended).
 //
 // GEMMs run on the matrix cores.  A 256-thread block owns a 128x128 output tile: four
 // waves of 64x64, each 2x2 MFMA tiles of 32x32.  The reduction advances in k-tiles of 32
-// staged through LDS, with the next k-tile's global loads in flight during the current
-// one's MFMAs.  fp32 compute: v_mfma_f32_32x32x2f32 on fp32 operands; bf16 compute:
+// staged through two LDS buffers (one barrier per k-tile), with the next k-tile's global
+// loads in flight during the current one's MFMAs.  fp32 compute: v_mfma_f32_32x32x2f32 on fp32 operands; bf16 compute:
 // v_mfma_f32_32x32x16_bf16 on operands rounded to bf16 nearest-even as they enter LDS.
 // Both accumulate in fp32.  The weight gradient reduces over the batch: when its output
 // tiles are too few to fill the chip, the reduction is split over grid.z into fp32 partials
@@ -37,17 +41,23 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kBM = 128, kBN = 128, kBK = 32;
 constexpr int kGemmThreads = 256;
-constexpr int kColRows = 64;          // rows per block of the ReLU-backward / bias pass
 constexpr int kHeadThreads = 1024;
 
-enum Epilogue { kStore = 0, kBiasAct = 1, kSgd = 2, kPartial = 3 };
+// kSgd: C -= lr * acc (W, and the bias column), or, in a split reduction (gridDim.z > 1),
+// the slice's partial sums at C[(z * M + m) * ldc + n].
+enum Epilogue { kStore = 0, kBiasAct = 1, kSgd = 2 };
 
 // C[m, n] (m < M, n < N) from A[m, k] and B[k, n] (k < K):
 //   A[m, k] = AK ? A[m * lda + k] : A[k * lda + m]
 //   B[k, n] = BK ? B[n * ldb + k] : B[k * ldb + n]
-//   C[m, n] at C[m * ldc + n]; kPartial: slice z at C[(z * M + m) * ldc + n]
+//   C[m, n] at C[m * ldc + n]
+// A is fp32 (ASRC = kPlain) or bf16 (kPlainBF16, widened exactly as it is loaded).  B may
+// have a row of ones: B[k, n] = 1 for n == ones_col (the bias column of the weight
+// gradient).
+enum Source { kPlain = 0, kPlainBF16 = 1 };
+
 struct GemmArgs {
-  const float* A;
+  const void* A;       // fp32 or bf16 (ASRC)
   int64_t lda;
   const float* B;
   int64_t ldb;
@@ -60,61 +70,119 @@ struct GemmArgs {
   int64_t k_split;     // reduction length per grid.z slice, a multiple of kBK
   int64_t n_tiles;     // output tiles along n (the block index runs along n first)
   int vec_a, vec_b;    // operand 16-byte aligned with a stride that is a multiple of 4
+  int64_t ones_col;    // B: the column n that reads 1 (-1: none)
+  int64_t wcols;       // kSgd: C columns n < wcols are W[m, n]; n == wcols is the bias b[m]
+  float* bias_out;     //   (a split reduction writes both to the partial rows)
 };
 
-// Operand P[r, k] (r < rows, k < kend): KMAJ ? P[r * ld + k] : P[k * ld + r].  Thread t
-// loads 16 elements of the 128 x 32 tile at (r0, k0), four runs of 4 along the contiguous
-// direction: KMAJ: rows (t >> 3) + 32 q, columns 4 (t & 7) + e; otherwise rows 4 (t & 31) + e,
-// columns (t >> 5) + 8 q; slot 4 q + e.  Elements outside the operand are zero.
-template <bool KMAJ>
-__device__ __forceinline__ void load_tile(const float* __restrict__ P, int64_t ld,
-                                          int64_t rows, int64_t kend, int64_t r0, int64_t k0,
-                                          bool vec, float (&v)[16]) {
+// Operand P[r, k] (r < rows, k < kend): KMAJ ? P[r * ld + k] : P[k * ld + r], fp32 or bf16
+// (SRC).  Each thread loads 16 elements of the 128 x 32 tile at (r0, k0) so that every load
+// instruction reads consecutive addresses across the wavefront:
+//   KMAJ: four runs of 4 consecutive k, row (t >> 3) + 32 q, columns 4 (t & 7) .. +4
+//         (one 16-byte or 8-byte load per run when the operand allows it);
+//   else: row t & 127 and the 16 consecutive k from 16 (t >> 7), one load each (the lanes
+//         of a wavefront read 64 consecutive rows).
+// Elements outside the operand are zero, except that row `ones` reads 1.
+struct Src {
+  const void* p;
+  int64_t ld, rows, ones;
+  int vec;
+};
+
+template <int SRC>
+__device__ __forceinline__ float fetch1(const Src& o, int64_t off) {
+  if constexpr (SRC == kPlainBF16)
+    return __uint_as_float((uint32_t)static_cast<const uint16_t*>(o.p)[off] << 16);
+  else
+    return static_cast<const float*>(o.p)[off];
+}
+
+template <int SRC>
+__device__ __forceinline__ void fetch4(const Src& o, int64_t off, float* v) {
+  if constexpr (SRC == kPlainBF16) {
+    const uint2 h = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(o.p) + off);
+    v[0] = bf16_lo(h.x); v[1] = bf16_hi(h.x); v[2] = bf16_lo(h.y); v[3] = bf16_hi(h.y);
+  } else {
+    const float4 x = *reinterpret_cast<const float4*>(static_cast<const float*>(o.p) + off);
+    v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w;
+  }
+}
+
+template <bool KMAJ, int SRC>
+__device__ __forceinline__ void load_tile(const Src& o, int64_t kend, int64_t r0, int64_t k0,
+                                          float (&v)[16]) {
   const int t = threadIdx.x;
+  if constexpr (KMAJ) {
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int64_t r = KMAJ ? r0 + (t >> 3) + 32 * q : r0 + 4 * (t & 31);
-    const int64_t k = KMAJ ? k0 + 4 * (t & 7) : k0 + (t >> 5) + 8 * q;
-    const bool full = KMAJ ? (r < rows && k + 3 < kend) : (r + 3 < rows && k < kend);
-    if (vec && full) {
-      const float4 x = *reinterpret_cast<const float4*>(KMAJ ? P + r * ld + k : P + k * ld + r);
-      v[4 * q] = x.x;
-      v[4 * q + 1] = x.y;
-      v[4 * q + 2] = x.z;
-      v[4 * q + 3] = x.w;
+    for (int q = 0; q < 4; ++q) {
+      const int64_t r = r0 + (t >> 3) + 32 * q;
+      const int64_t k = k0 + 4 * (t & 7);
+      if (o.vec && r < o.rows && k + 3 < kend) {
+        fetch4<SRC>(o, r * o.ld + k, v + 4 * q);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          v[4 * q + e] = (r < o.rows && k + e < kend) ? fetch1<SRC>(o, r * o.ld + k + e) : 0.f;
+      }
+    }
+  } else {
+    const int64_t r = r0 + (t & 127);
+    const int64_t k = k0 + 16 * (t >> 7);
+    const bool rv = r < o.rows;
+    const float outside = r == o.ones ? 1.f : 0.f;
+    int64_t off = k * o.ld + r;
+    if (rv && k + 16 <= kend) {               // the whole run is inside the operand
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        v[j] = fetch1<SRC>(o, off);
+        off += o.ld;
+      }
     } else {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int64_t rr = KMAJ ? r : r + e, kk = KMAJ ? k + e : k;
-        v[4 * q + e] = (rr < rows && kk < kend) ? P[KMAJ ? rr * ld + kk : kk * ld + rr] : 0.f;
+      for (int j = 0; j < 16; ++j) {
+        v[j] = (k + j < kend) ? (rv ? fetch1<SRC>(o, off) : outside) : 0.f;
+        off += o.ld;
       }
     }
   }
 }
 
 // The tile in LDS as [128 rows][PITCH], k contiguous, in the compute type (the conversion to
-// bf16 is the nearest-even rounding of the operand).
+// bf16 is the nearest-even rounding of the operand).  Rows are 16-byte aligned: the KMAJ
+// runs go out as one 8-byte (bf16) or 16-byte (fp32) store, the 16-k runs as 16-byte stores.
+template <typename LT>
+__device__ __forceinline__ void put(LT* dst, const float* x, int n) {
+  if constexpr (std::is_same<LT, float>::value) {
+    for (int i = 0; i < n; i += 4)
+      *reinterpret_cast<float4*>(dst + i) = make_float4(x[i], x[i + 1], x[i + 2], x[i + 3]);
+  } else {
+    for (int i = 0; i < n; i += 4) {
+      typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+      bf16x4 h = {(__bf16)x[i], (__bf16)x[i + 1], (__bf16)x[i + 2], (__bf16)x[i + 3]};
+      *reinterpret_cast<bf16x4*>(dst + i) = h;
+    }
+  }
+}
+
 template <bool KMAJ, typename LT, int PITCH>
 __device__ __forceinline__ void store_tile(LT* __restrict__ lds, const float (&v)[16]) {
   const int t = threadIdx.x;
+  if constexpr (KMAJ) {
 #pragma unroll
-  for (int q = 0; q < 4; ++q)
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int r = KMAJ ? (t >> 3) + 32 * q : 4 * (t & 31) + e;
-      const int k = KMAJ ? 4 * (t & 7) + e : (t >> 5) + 8 * q;
-      lds[r * PITCH + k] = (LT)v[4 * q + e];
-    }
+    for (int q = 0; q < 4; ++q) put<LT>(lds + ((t >> 3) + 32 * q) * PITCH + 4 * (t & 7), v + 4 * q, 4);
+  } else {
+    put<LT>(lds + (t & 127) * PITCH + 16 * (t >> 7), v, 16);
+  }
 }
 
-template <bool BF, bool AK, bool BK, int EPI>
+template <bool BF, bool AK, bool BK, int EPI, int ASRC>
 __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(GemmArgs g) {
   using LT = typename std::conditional<BF, __bf16, float>::type;
-  // bf16 rows stay 16-byte aligned for the 8-element fragment reads; fp32 rows are padded
-  // by one word against bank conflicts of the column-wise fragment reads
-  constexpr int PITCH = BF ? kBK + 8 : kBK + 1;
-  __shared__ LT As[kBM * PITCH];
-  __shared__ LT Bs[kBN * PITCH];
+  // rows of 16-byte multiples, padded against bank conflicts of the fragment reads
+  constexpr int PITCH = BF ? kBK + 8 : kBK + 4;
+  constexpr int TILE = kBM * PITCH;
+  __shared__ __attribute__((aligned(16))) LT As[2 * TILE];   // two buffers: one barrier
+  __shared__ __attribute__((aligned(16))) LT Bs[2 * TILE];   // per k-tile
 
   const int64_t tile = blockIdx.x;
   const int64_t n0 = (tile % g.n_tiles) * kBN;
@@ -132,19 +200,25 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(GemmArgs g) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
+  const Src sa{g.A, g.lda, g.M, -1, g.vec_a};
+  const Src sb{g.B, g.ldb, g.ones_col >= 0 ? g.ones_col : g.N, g.ones_col, g.vec_b};
   float va[16], vb[16];
+  int cur = 0;
   if (kb < ke) {
-    load_tile<AK>(g.A, g.lda, g.M, ke, m0, kb, g.vec_a, va);
-    load_tile<BK>(g.B, g.ldb, g.N, ke, n0, kb, g.vec_b, vb);
-  }
-  for (int64_t k0 = kb; k0 < ke; k0 += kBK) {
+    load_tile<AK, ASRC>(sa, ke, m0, kb, va);
+    load_tile<BK, kPlain>(sb, ke, n0, kb, vb);
     store_tile<AK, LT, PITCH>(As, va);
     store_tile<BK, LT, PITCH>(Bs, vb);
-    __syncthreads();
-    if (k0 + kBK < ke) {                 // next k-tile's loads overlap this tile's MFMAs
-      load_tile<AK>(g.A, g.lda, g.M, ke, m0, k0 + kBK, g.vec_a, va);
-      load_tile<BK>(g.B, g.ldb, g.N, ke, n0, k0 + kBK, g.vec_b, vb);
+  }
+  __syncthreads();
+  for (int64_t k0 = kb; k0 < ke; k0 += kBK) {
+    const bool more = k0 + kBK < ke;
+    if (more) {                          // next k-tile's loads overlap this tile's MFMAs
+      load_tile<AK, ASRC>(sa, ke, m0, k0 + kBK, va);
+      load_tile<BK, kPlain>(sb, ke, n0, k0 + kBK, vb);
     }
+    const LT* Ac = As + cur * TILE;
+    const LT* Bc = Bs + cur * TILE;
     if constexpr (BF) {
       // fragment: lane holds row rl, k = 16 s + 8 kg .. +8 (A: rows m, B: rows n of Bs)
 #pragma unroll
@@ -152,11 +226,11 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(GemmArgs g) {
         bf16x8 a[2], b[2];
 #pragma unroll
         for (int i = 0; i < 2; ++i)
-          a[i] = *reinterpret_cast<const bf16x8*>(As + (64 * wm + 32 * i + rl) * PITCH +
+          a[i] = *reinterpret_cast<const bf16x8*>(Ac + (64 * wm + 32 * i + rl) * PITCH +
                                                   16 * s + 8 * kg);
 #pragma unroll
         for (int j = 0; j < 2; ++j)
-          b[j] = *reinterpret_cast<const bf16x8*>(Bs + (64 * wn + 32 * j + rl) * PITCH +
+          b[j] = *reinterpret_cast<const bf16x8*>(Bc + (64 * wn + 32 * j + rl) * PITCH +
                                                   16 * s + 8 * kg);
 #pragma unroll
         for (int i = 0; i < 2; ++i)
@@ -170,9 +244,9 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(GemmArgs g) {
       for (int s = 0; s < kBK / 2; ++s) {
         float a[2], b[2];
 #pragma unroll
-        for (int i = 0; i < 2; ++i) a[i] = As[(64 * wm + 32 * i + rl) * PITCH + 2 * s + kg];
+        for (int i = 0; i < 2; ++i) a[i] = Ac[(64 * wm + 32 * i + rl) * PITCH + 2 * s + kg];
 #pragma unroll
-        for (int j = 0; j < 2; ++j) b[j] = Bs[(64 * wn + 32 * j + rl) * PITCH + 2 * s + kg];
+        for (int j = 0; j < 2; ++j) b[j] = Bc[(64 * wn + 32 * j + rl) * PITCH + 2 * s + kg];
 #pragma unroll
         for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -180,7 +254,12 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(GemmArgs g) {
             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[i], b[j], acc[i][j], 0, 0, 0);
       }
     }
+    if (more) {                          // the other buffer was last read before the
+      store_tile<AK, LT, PITCH>(As + (cur ^ 1) * TILE, va);   // previous barrier
+      store_tile<BK, LT, PITCH>(Bs + (cur ^ 1) * TILE, vb);
+    }
     __syncthreads();
+    cur ^= 1;
   }
 
   // acc[i][j][v] = C[m, n]: m = 8 (v / 4) + 4 kg + v % 4 and n = rl within the 32x32 tile
@@ -203,63 +282,54 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(GemmArgs g) {
           x += bn;
           if (g.relu) x = x > 0.f ? x : 0.f;
           g.C[m * g.ldc + n] = x;
-        } else if constexpr (EPI == kSgd) {
-          float* c = g.C + m * g.ldc + n;
-          *c = __builtin_fmaf(-g.lr, x, *c);
         } else {
-          g.C[((int64_t)blockIdx.z * g.M + m) * g.ldc + n] = x;
+          if (gridDim.z > 1) {           // a slice of a split reduction: its partial sum
+            g.C[((int64_t)blockIdx.z * g.M + m) * g.ldc + n] = x;
+          } else {
+            float* c = n < g.wcols ? g.C + m * g.ldc + n : g.bias_out + m;
+            *c = __builtin_fmaf(-g.lr, x, *c);
+          }
         }
       }
     }
 }
 
-// W[i] -= lr * (sum over the S slices of part[s * count + i]), slices in order.
+// The update from the split weight gradient: part[s] is [N, cols] (cols = K, plus the bias
+// column K when b is given); element (n, c) is summed over the S slices in order and applied
+// to W[n, c] (c < K) or b[n] (c == K).
 __global__ __launch_bounds__(256) void sgd_from_partials_kernel(
-    const float* __restrict__ part, int64_t count, int S, float lr, float* __restrict__ W) {
+    const float* __restrict__ part, int64_t N, int64_t K, int64_t cols, int S, float lr,
+    float* __restrict__ W, float* __restrict__ b) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t count = N * cols;
   if (i >= count) return;
   float s = 0.f;
   for (int z = 0; z < S; ++z) s += part[z * count + i];
-  W[i] = __builtin_fmaf(-lr, s, W[i]);
+  const int64_t n = i / cols, c = i - n * cols;
+  float* t = c < K ? W + n * K + c : b + n;
+  *t = __builtin_fmaf(-lr, s, *t);
 }
 
-// dA[m, n] = dY[m, n] * [Y[m, n] > 0] (or dY), contiguous [M, N]; colpart[chunk, n] = the
-// sum of the chunk's kColRows rows of dA, over four interleaved accumulators.
-template <bool DYB>
-__global__ __launch_bounds__(256) void relu_bwd_kernel(
-    const void* __restrict__ dY, int64_t dys, const float* __restrict__ Y, int64_t ys,
-    int64_t M, int64_t N, int relu, float* __restrict__ dA, float* __restrict__ colpart) {
-  // block = (column block, row chunk), column blocks fastest
-  const int64_t cb = (N + 255) / 256;
-  const int64_t chunk = (int64_t)blockIdx.x / cb;
-  const int64_t n = ((int64_t)blockIdx.x % cb) * 256 + threadIdx.x;
-  if (n >= N) return;
-  const int64_t mb = chunk * kColRows;
-  const int64_t me = M < mb + kColRows ? M : mb + kColRows;
-  float s[4] = {0.f, 0.f, 0.f, 0.f};
-  for (int64_t m = mb; m < me; ++m) {
-    float gv;
-    if constexpr (DYB)
-      gv = __uint_as_float((uint32_t)static_cast<const uint16_t*>(dY)[m * dys + n] << 16);
-    else
-      gv = static_cast<const float*>(dY)[m * dys + n];
-    if (relu && !(Y[m * ys + n] > 0.f)) gv = 0.f;
-    dA[m * N + n] = gv;
-    s[(m - mb) & 3] += gv;
-  }
-  colpart[chunk * N + n] = (s[0] + s[1]) + (s[2] + s[3]);
-}
-
-// b[n] -= lr * (sum over chunks of colpart[c, n]), over eight interleaved accumulators.
-__global__ __launch_bounds__(256) void bias_sgd_kernel(const float* __restrict__ colpart,
-                                                       int64_t chunks, int64_t N, float lr,
-                                                       float* __restrict__ b) {
-  const int64_t n = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (n >= N) return;
-  float s[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  for (int64_t c = 0; c < chunks; ++c) s[c & 7] += colpart[c * N + n];
-  const float t = ((s[0] + s[1]) + (s[2] + s[3])) + ((s[4] + s[5]) + (s[6] + s[7]));
-  b[n] = __builtin_fmaf(-lr, t, b[n]);
+// dA[m, n] = dY[m, n] * [Y[m, n] > 0], contiguous [M, N], fp32 or bf16 nearest-even (OUTB).
+template <bool DYB, bool OUTB>
+__global__ __launch_bounds__(256) void relu_grad_kernel(const void* __restrict__ dY, int64_t dys,
+                                                        const float* __restrict__ Y, int64_t ys,
+                                                        int64_t M, int64_t N,
+                                                        void* __restrict__ dA) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= M * N) return;
+  const int64_t m = i / N, n = i - m * N;
+  float gv;
+  if constexpr (DYB)
+    gv = __uint_as_float((uint32_t)static_cast<const uint16_t*>(dY)[m * dys + n] << 16);
+  else
+    gv = static_cast<const float*>(dY)[m * dys + n];
+  const float yv = Y[m * ys + n];
+  gv = yv > 0.f ? gv : 0.f;
+  if constexpr (OUTB)
+    static_cast<__bf16*>(dA)[i] = (__bf16)gv;
+  else
+    static_cast<float*>(dA)[i] = gv;
 }
 
 // The logistic head over M logits (one block): p = sigmoid(s), the cross-entropy
@@ -303,20 +373,20 @@ __global__ __launch_bounds__(kHeadThreads) void logistic_ne_kernel(
   }
 }
 
-bool vec_ok(const float* p, int64_t ld) {
-  return ((uintptr_t)p & 15) == 0 && (ld & 3) == 0;
+bool vec_ok(const void* p, int64_t ld, int elem_bytes) {
+  return ((uintptr_t)p & (4 * elem_bytes - 1)) == 0 && (ld & 3) == 0;
 }
 
-template <bool AK, bool BK, int EPI>
+template <bool AK, bool BK, int EPI, int ASRC>
 hipError_t launch_gemm(bool bf16, GemmArgs g, int splits, hipStream_t s) {
   g.n_tiles = (g.N + kBN - 1) / kBN;
   const int64_t tiles = g.n_tiles * ((g.M + kBM - 1) / kBM);
   if (tiles == 0) return hipSuccess;
   const dim3 grid((unsigned)tiles, 1, (unsigned)splits);
   if (bf16)
-    gemm_kernel<true, AK, BK, EPI><<<grid, kGemmThreads, 0, s>>>(g);
+    gemm_kernel<true, AK, BK, EPI, ASRC><<<grid, kGemmThreads, 0, s>>>(g);
   else
-    gemm_kernel<false, AK, BK, EPI><<<grid, kGemmThreads, 0, s>>>(g);
+    gemm_kernel<false, AK, BK, EPI, ASRC><<<grid, kGemmThreads, 0, s>>>(g);
   return hipGetLastError();
 }
 
@@ -325,10 +395,11 @@ size_t round256(size_t b) { return (b + 255) & ~(size_t)255; }
 }  // namespace
 
 // Slices of the weight-gradient reduction over the M batch rows: none while the output
-// tiles alone give a block per compute unit, else enough for about two blocks per unit,
-// each slice at least 512 rows long.  *k_split: rows per slice (a multiple of the k-tile).
-int dense_wgrad_splits(int64_t M, int N, int K, int64_t* k_split) {
-  const int64_t tiles = (int64_t)((N + kBM - 1) / kBM) * ((K + kBN - 1) / kBN);
+// tiles (N rows by `cols` columns) alone give a block per compute unit, else enough for
+// about two blocks per unit, each slice at least 512 rows long.  *k_split: rows per slice
+// (a multiple of the k-tile).
+int dense_wgrad_splits(int64_t M, int N, int cols, int64_t* k_split) {
+  const int64_t tiles = (int64_t)((N + kBM - 1) / kBM) * ((cols + kBN - 1) / kBN);
   int64_t S = 1;
   if (tiles < 256) {
     S = (512 + tiles - 1) / tiles;
@@ -344,13 +415,14 @@ int dense_wgrad_splits(int64_t M, int N, int K, int64_t* k_split) {
   return (int)S;
 }
 
-size_t dense_bwd_workspace_bytes(int64_t M, int N, int K) {
-  const int64_t chunks = (M + kColRows - 1) / kColRows;
-  const int S = dense_wgrad_splits(M, N, K, nullptr);
-  size_t b = round256((size_t)M * N * sizeof(float)) +
-             round256((size_t)chunks * N * sizeof(float));
-  if (S > 1) b += round256((size_t)S * N * K * sizeof(float));
-  return b;
+// Workspace of the backward: dA (ReLU layers: M * N in the compute type), then the split
+// reduction's partials.
+size_t dense_bwd_workspace_bytes(int64_t M, int N, int K, bool bias, bool relu, bool bf16) {
+  const int cols = K + (bias ? 1 : 0);
+  const int S = dense_wgrad_splits(M, N, cols, nullptr);
+  const size_t da = relu ? round256((size_t)M * N * (bf16 ? 2 : 4)) : 0;
+  const size_t part = S > 1 ? round256((size_t)S * N * cols * sizeof(float)) : 0;
+  return da + part > 0 ? da + part : 256;
 }
 
 hipError_t launch_dense_fwd(const float* X, int64_t xs, int64_t M, int K, const float* W,
@@ -370,9 +442,10 @@ hipError_t launch_dense_fwd(const float* X, int64_t xs, int64_t M, int K, const 
   g.bias = b;
   g.relu = relu;
   g.k_split = ((int64_t)K + kBK - 1) / kBK * kBK;
-  g.vec_a = vec_ok(X, xs);
-  g.vec_b = vec_ok(W, K);
-  return launch_gemm<true, true, kBiasAct>(bf16, g, 1, s);
+  g.vec_a = vec_ok(X, xs, 4);
+  g.vec_b = vec_ok(W, K, 4);
+  g.ones_col = -1;
+  return launch_gemm<true, true, kBiasAct, kPlain>(bf16, g, 1, s);
 }
 
 hipError_t launch_dense_bwd_sgd(const float* X, int64_t xs, int64_t M, int K, float* W,
@@ -380,27 +453,45 @@ hipError_t launch_dense_bwd_sgd(const float* X, int64_t xs, int64_t M, int K, fl
                                 const void* dY, bool dy_bf16, int64_t dys, bool bf16, float lr,
                                 float* dX, int64_t dxs, void* workspace, hipStream_t s) {
   if (M == 0) return hipSuccess;
-  const int64_t chunks = (M + kColRows - 1) / kColRows;
   char* ws = static_cast<char*>(workspace);
-  float* dA = reinterpret_cast<float*>(ws);
-  float* colpart = reinterpret_cast<float*>(ws + round256((size_t)M * N * sizeof(float)));
-  float* part = reinterpret_cast<float*>(ws + round256((size_t)M * N * sizeof(float)) +
-                                         round256((size_t)chunks * N * sizeof(float)));
-  // 1. dA and the bias gradient's column partials
-  {
-    const unsigned grid = (unsigned)(((N + 255) / 256) * chunks);
-    if (dy_bf16)
-      relu_bwd_kernel<true><<<grid, 256, 0, s>>>(dY, dys, Y, ys, M, N, relu, dA, colpart);
+  // 1. the GEMMs' dA operand: dY itself for a linear layer, else dY * [Y > 0] written once
+  const void* dA = dY;
+  int64_t lda = dys;
+  bool a_bf16 = dy_bf16;
+  size_t used = 0;
+  if (relu) {
+    const int64_t count = M * (int64_t)N;
+    const unsigned blocks = (unsigned)((count + 255) / 256);
+    if (dy_bf16 && bf16)
+      relu_grad_kernel<true, true><<<blocks, 256, 0, s>>>(dY, dys, Y, ys, M, N, ws);
+    else if (dy_bf16)
+      relu_grad_kernel<true, false><<<blocks, 256, 0, s>>>(dY, dys, Y, ys, M, N, ws);
+    else if (bf16)
+      relu_grad_kernel<false, true><<<blocks, 256, 0, s>>>(dY, dys, Y, ys, M, N, ws);
     else
-      relu_bwd_kernel<false><<<grid, 256, 0, s>>>(dY, dys, Y, ys, M, N, relu, dA, colpart);
+      relu_grad_kernel<false, false><<<blocks, 256, 0, s>>>(dY, dys, Y, ys, M, N, ws);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
+    dA = ws;
+    lda = N;
+    a_bf16 = bf16;
+    used = round256((size_t)count * (bf16 ? 2 : 4));
   }
-  // 2. dX = dA W, with the weights before this step's update
+  auto gemm = [&](auto AK, auto BK, auto EPI, GemmArgs g, int splits) {
+    constexpr bool ak = decltype(AK)::value, bk = decltype(BK)::value;
+    constexpr int epi = decltype(EPI)::value;
+    return a_bf16 ? launch_gemm<ak, bk, epi, kPlainBF16>(bf16, g, splits, s)
+                  : launch_gemm<ak, bk, epi, kPlain>(bf16, g, splits, s);
+  };
+  using T = std::true_type;
+  using F = std::false_type;
+  using Store = std::integral_constant<int, kStore>;
+  using Sgd = std::integral_constant<int, kSgd>;
+  // 2. dX = dA W, with the weights before this step's update (A = dA rows, k = n)
   if (dX) {
     GemmArgs g{};
     g.A = dA;
-    g.lda = N;
+    g.lda = lda;
     g.B = W;
     g.ldb = K;
     g.M = M;
@@ -409,51 +500,46 @@ hipError_t launch_dense_bwd_sgd(const float* X, int64_t xs, int64_t M, int K, fl
     g.C = dX;
     g.ldc = dxs;
     g.k_split = ((int64_t)N + kBK - 1) / kBK * kBK;
-    g.vec_a = vec_ok(dA, N);
-    g.vec_b = vec_ok(W, K);
-    hipError_t e = launch_gemm<true, false, kStore>(bf16, g, 1, s);
+    g.vec_a = vec_ok(dA, lda, a_bf16 ? 2 : 4);
+    g.vec_b = vec_ok(W, K, 4);
+    g.ones_col = -1;
+    hipError_t e = gemm(T{}, F{}, Store{}, g, 1);
     if (e != hipSuccess) return e;
   }
-  // 3. W -= lr dA^T X: rows n of the layer's output, columns k of its input, reduced over m
-  {
-    int64_t ks = 0;
-    const int S = dense_wgrad_splits(M, N, K, &ks);
-    GemmArgs g{};
-    g.A = dA;
-    g.lda = N;
-    g.B = X;
-    g.ldb = xs;
-    g.M = N;
-    g.N = K;
-    g.K = M;
-    g.k_split = ks;
-    g.lr = lr;
-    g.vec_a = vec_ok(dA, N);
-    g.vec_b = vec_ok(X, xs);
-    hipError_t e;
-    if (S == 1) {
-      g.C = W;
-      g.ldc = K;
-      e = launch_gemm<false, false, kSgd>(bf16, g, 1, s);
-    } else {
-      g.C = part;
-      g.ldc = K;
-      e = launch_gemm<false, false, kPartial>(bf16, g, S, s);
-      if (e == hipSuccess) {
-        const int64_t count = (int64_t)N * K;
-        sgd_from_partials_kernel<<<(unsigned)((count + 255) / 256), 256, 0, s>>>(part, count, S,
-                                                                                 lr, W);
-        e = hipGetLastError();
-      }
-    }
-    if (e != hipSuccess) return e;
+  // 3. [W | b] -= lr dA^T [X | 1]: rows n of the layer's output, columns k of its input and
+  //    the bias column K, reduced over the m rows (A[n, m] = dA[m, n], B[m, k] = X[m, k])
+  const int cols = K + (b ? 1 : 0);
+  int64_t ks = 0;
+  const int S = dense_wgrad_splits(M, N, cols, &ks);
+  GemmArgs g{};
+  g.A = dA;
+  g.lda = lda;
+  g.B = X;
+  g.ldb = xs;
+  g.M = N;
+  g.N = cols;
+  g.K = M;
+  g.k_split = ks;
+  g.lr = lr;
+  g.vec_a = 0;                         // the transposed operands load one element per lane
+  g.vec_b = 0;
+  g.ones_col = b ? K : -1;
+  g.wcols = K;
+  g.bias_out = b;
+  if (S == 1) {
+    g.C = W;
+    g.ldc = K;
+    return gemm(F{}, F{}, Sgd{}, g, 1);
   }
-  // 4. b -= lr sum_m dA
-  if (b) {
-    bias_sgd_kernel<<<(unsigned)((N + 255) / 256), 256, 0, s>>>(colpart, chunks, N, lr, b);
-    return hipGetLastError();
-  }
-  return hipSuccess;
+  float* part = reinterpret_cast<float*>(ws + used);
+  g.C = part;
+  g.ldc = cols;
+  hipError_t e = gemm(F{}, F{}, Sgd{}, g, S);
+  if (e != hipSuccess) return e;
+  const int64_t count = (int64_t)N * cols;
+  sgd_from_partials_kernel<<<(unsigned)((count + 255) / 256), 256, 0, s>>>(part, N, K, cols, S,
+                                                                           lr, W, b);
+  return hipGetLastError();
 }
 
 hipError_t launch_logistic_ne(const float* logits, int64_t ls, const float* labels, int64_t M,

@@ -448,13 +448,15 @@ def _rows(t: torch.Tensor, name: str):
     return t.shape[0], t.shape[1], t.stride(0)
 
 
-def dense_bwd_workspace_bytes(M: int, K: int, N: int) -> int:
+def dense_bwd_workspace_bytes(M: int, K: int, N: int, bias: bool = True, relu: bool = True,
+                              compute: int = CTR_F32) -> int:
     """Workspace of ctr_dense_bwd_sgd for M rows of a K -> N layer (the two-call query)."""
     wsb = ctypes.c_size_t(0)
-    _check("ctr_dense_bwd_sgd", load().ctr_dense_bwd_sgd(None, K, M, K, None, None, N, 0, None,
-                                                         N, None, CTR_F32, N, CTR_F32, 0.0,
-                                                         None, K, None, ctypes.byref(wsb),
-                                                         None))
+    b = ctypes.c_void_p(16) if bias else None       # only its presence matters to the query
+    _check("ctr_dense_bwd_sgd", load().ctr_dense_bwd_sgd(None, K, M, K, None, b, N,
+                                                         int(bool(relu)), None, N, None,
+                                                         CTR_F32, N, compute, 0.0, None, K,
+                                                         None, ctypes.byref(wsb), None))
     return wsb.value
 
 
@@ -487,7 +489,8 @@ def ctr_dense_bwd_sgd(X: torch.Tensor, W: torch.Tensor, b: Optional[torch.Tensor
     ys = _rows(Y, "Y")[2] if Y is not None else N
     dxs = _rows(dX, "dX")[2] if dX is not None else K
     if workspace is None:
-        workspace = _workspace(dense_bwd_workspace_bytes(M, K, N), X.device)
+        workspace = _workspace(dense_bwd_workspace_bytes(M, K, N, b is not None, relu,
+                                                         compute), X.device)
     wsb = ctypes.c_size_t(workspace.numel())
     args = (_ptr(X), xs, M, K, _ptr(W), _ptr(b), N, int(bool(relu)), _ptr(Y), ys, _ptr(dY),
             _dtype_code(dY), dys, compute, float(lr), _ptr(dX), dxs, _ptr(workspace),

@@ -70,7 +70,8 @@ class DlrmStep:
         # gradients of each layer's input (top: the first writes the front end's dR)
         self.t_dx = [self.fe.dR] + [torch.empty((B, L.K), device=dv) for L in self.top[1:]]
         self.b_dx = [None] + [torch.empty((B, L.K), device=dv) for L in self.bottom[1:]]
-        ws = max(ctr.dense_bwd_workspace_bytes(B, L.K, L.N) for L in self.bottom + self.top)
+        ws = max(ctr.dense_bwd_workspace_bytes(B, L.K, L.N, True, L.relu, self.compute)
+                 for L in self.bottom + self.top)
         self.ws = torch.empty(max(ws, 256), dtype=torch.uint8, device=dv)
         self._prepare()
 

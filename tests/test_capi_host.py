@@ -291,8 +291,14 @@ def test_dense_and_head_bad_args():
     wsb = ctypes.c_size_t(0)
     assert lib.ctr_dense_bwd_sgd(None, 13, 10, 13, None, None, 4, 1, None, 4, None, 0, 4, 0,
                                  0.1, None, 13, None, ctypes.byref(wsb), None) == ctr.CTR_OK
-    assert wsb.value >= 10 * 4 * 4
-    assert wsb.value == ctr.dense_bwd_workspace_bytes(10, 13, 4)
+    assert wsb.value >= 10 * 4 * 4                                    # dA of a ReLU layer
+    assert wsb.value == ctr.dense_bwd_workspace_bytes(10, 13, 4, bias=False)
+    # bf16 compute keeps dA in bf16; a linear layer needs no dA
+    assert ctr.dense_bwd_workspace_bytes(1000, 13, 64, compute=ctr.CTR_BF16) < \
+        ctr.dense_bwd_workspace_bytes(1000, 13, 64)
+    assert ctr.dense_bwd_workspace_bytes(1000, 13, 64, relu=False) < 1000 * 64 * 2
+    # a split reduction (few output tiles, many rows) needs its partials
+    assert ctr.dense_bwd_workspace_bytes(100000, 64, 64, relu=False) >= 2 * 64 * 65 * 4
 
     def bw(ws, size, **kw):
         a = dict(dt=0, dys=4, relu=1, Y=FAKE, dX=None, dxs=13)
@@ -302,7 +308,7 @@ def test_dense_and_head_bad_args():
                                      a["dt"], a["dys"], 0, 0.1, a["dX"], a["dxs"], ws,
                                      ctypes.byref(s), None)
 
-    assert bw(FAKE, 16) == ctr.CTR_ERR_WORKSPACE_TOO_SMALL
+    assert bw(FAKE, 8) == ctr.CTR_ERR_WORKSPACE_TOO_SMALL
     assert bw(MISALIGNED, wsb.value) == ctr.CTR_ERR_UNSUPPORTED
     assert bw(FAKE, wsb.value, dt=3) == ctr.CTR_ERR_INVALID_ARGUMENT
     assert bw(FAKE, wsb.value, dys=2) == ctr.CTR_ERR_INVALID_ARGUMENT

@@ -180,3 +180,20 @@ def test_logistic_base_rate_gives_ne_one():
     s = np.full(M, np.log(0.3 / 0.7), np.float32)
     st = host(ctr.ctr_logistic_ne(dev(s), dev(y)))
     assert abs(st[2] - 1.0) < 1e-5
+
+
+def test_dense_bwd_linear_layer_needs_no_output():
+    """A linear layer's backward reads no Y: passing none gives the same bits."""
+    rng = np.random.default_rng(9)
+    M, K, N = 700, 96, 40
+    X, W, b = _layer(rng, M, K, N)
+    dY = dev(rng.standard_normal((M, N)).astype(np.float32))
+    outs = []
+    for with_y in (True, False):
+        Wd, bd = dev(W), dev(b)
+        Y = ctr.ctr_dense_fwd(dev(X), Wd, bd, False, BF16) if with_y else None
+        dX = torch.empty((M, K), device=DEV)
+        ctr.ctr_dense_bwd_sgd(dev(X), Wd, bd, False, Y, dY, 0.02, BF16, dX)
+        outs.append((host(Wd), host(bd), host(dX)))
+    for a, c in zip(*outs):
+        np.testing.assert_array_equal(a, c)
