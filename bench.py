@@ -356,6 +356,61 @@ def _cpu_baseline(w, seconds, orc, np, workloads):
             "seconds_per_step": el / reps}
 
 
+def cpu_baseline_mlp(w, seconds: float):
+    """The oracle's MLPs and logistic head (forward, backward and every parameter step) on
+    the first samples of the batch, repeated until `seconds`; samples per second."""
+    import numpy as np
+    from oracle import oracle as orc
+
+    from sparse_embedding_lookup_amd import workloads
+
+    inp = workloads.dlrm_inputs(w)
+    R_all = np.random.default_rng(5).standard_normal((min(w.batch, 2048), w.dim + w.P))
+    bf16 = w.compute == "bf16"
+    nb, nt = len(inp.bottom), len(inp.top)
+
+    def one(b):
+        X0 = inp.dense_raw[:b].astype(np.float64)
+        R = R_all[:b]
+        y = inp.labels[:b]
+        acts, x = [], X0
+        for i, (W, bb) in enumerate(inp.bottom):
+            out, _ = orc.dense_fwd(x, W, bb, True, bf16)
+            acts.append((x, out))
+            x = out
+        x = R
+        for i, (W, bb) in enumerate(inp.top):
+            out, _ = orc.dense_fwd(x, W, bb, i < nt - 1, bf16)
+            acts.append((x, out))
+            x = out
+        _, dy, _, _, _ = orc.logistic_ne(x[:, 0], y)
+        dy = dy[:, None]
+        for i in reversed(range(nt)):
+            x, out = acts[nb + i]
+            W, bb = inp.top[i]
+            dy = orc.dense_bwd_sgd(x, W, bb, i < nt - 1, out, dy, bf16, w.lr)["dX"]
+        dy = dy[:, :w.dim]                     # the dense slot's share of dR (a stand-in)
+        for i in reversed(range(nb)):
+            x, out = acts[i]
+            W, bb = inp.bottom[i]
+            dy = orc.dense_bwd_sgd(x, W, bb, True, out, dy, bf16, w.lr, want_dx=i > 0).get("dX")
+
+    t0 = time.perf_counter()                   # size the sample from a 16-sample pass
+    one(16)
+    b = int(min(R_all.shape[0], max(16, 16 * 0.5 * seconds / (time.perf_counter() - t0))))
+    reps = 0
+    t0 = time.perf_counter()
+    while True:
+        one(b)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds or reps >= 1000:
+            break
+    return {"value": reps * b / el, "unit": "samples/s (MLPs + head, forward and backward)",
+            "cores": orc.get_threads(), "kind": "oracle",
+            "sample": "%d oracle pass(es) over the first %d samples in %.1f s" % (reps, b, el)}
+
+
 def bench_dictionary(args):
     """One step = the inference lookup of one batch: ctr_dict_lookup (raw ID -> value) then
     ctr_dict_embbag_fwd (pooled rows, one ID per (sample, slot) bag).  `value` is measured
@@ -710,6 +765,10 @@ def main():
     if w.interaction and args.dlrm:
         print("[bench] timing the whole DLRM step", file=sys.stderr, flush=True)
         dlrm = time_dlrm(fe, w, K)
+        dlrm["mlp_samples_per_s"] = w.batch / (dlrm["mlp_ms"] * 1e-3)
+        if not args.no_cpu:
+            print("[bench] CPU oracle of the MLPs", file=sys.stderr, flush=True)
+            dlrm["cpu_baseline_mlp"] = cpu_baseline_mlp(w, min(args.cpu_seconds, 8.0))
 
     step_bytes = sum(byts.values())
     value = w.nnz / (ms_step * 1e-3)
