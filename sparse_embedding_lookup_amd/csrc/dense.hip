@@ -39,8 +39,14 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-constexpr int kBM = 128, kBN = 128, kBK = 32;
+constexpr int kBM = 128, kBN = 128;
+// k-tile: 32.  A 64-wide bf16 k-tile doubles the bytes in flight per barrier, but its LDS
+// (2 x 2 x 128 x 72 bf16) and registers leave two blocks per CU instead of three: the
+// forward on a 32768 x 2208 x 1024 layer went from 0.364 to 0.433 ms.  With a transposed
+// operand (KT/2 loads per thread) it would run one wave per SIMD.
+__host__ __device__ constexpr int k_tile(bool, bool, bool) { return 32; }
 constexpr int kGemmThreads = 256;
+constexpr int kXcds = 8;              // accelerator complex dies of the MI355X
 constexpr int kHeadThreads = 1024;
 
 // kSgd: C -= lr * acc (W, and the bias column), or, in a split reduction (gridDim.z > 1),
@@ -67,7 +73,7 @@ struct GemmArgs {
   const float* bias;   // kBiasAct, nullable
   int relu;            // kBiasAct
   float lr;            // kSgd
-  int64_t k_split;     // reduction length per grid.z slice, a multiple of kBK
+  int64_t k_split;     // reduction length per grid.z slice, a multiple of the k-tile
   int64_t n_tiles;     // output tiles along n (the block index runs along n first)
   int vec_a, vec_b;    // operand 16-byte aligned with a stride that is a multiple of 4
   int64_t ones_col;    // B: the column n that reads 1 (-1: none)
@@ -76,12 +82,12 @@ struct GemmArgs {
 };
 
 // Operand P[r, k] (r < rows, k < kend): KMAJ ? P[r * ld + k] : P[k * ld + r], fp32 or bf16
-// (SRC).  Each thread loads 16 elements of the 128 x 32 tile at (r0, k0) so that every load
-// instruction reads consecutive addresses across the wavefront:
-//   KMAJ: four runs of 4 consecutive k, row (t >> 3) + 32 q, columns 4 (t & 7) .. +4
-//         (one 16-byte or 8-byte load per run when the operand allows it);
-//   else: row t & 127 and the 16 consecutive k from 16 (t >> 7), one load each (the lanes
-//         of a wavefront read 64 consecutive rows).
+// (SRC).  Each thread loads KT/2 elements of the 128 x KT tile at (r0, k0) so that every
+// load instruction reads consecutive addresses across the wavefront:
+//   KMAJ: KT/8 runs of 4 consecutive k; KT/4 lanes share a row (one 16-byte or 8-byte load
+//         per run when the operand allows it);
+//   else: row t & 127 and the KT/2 consecutive k from (KT/2)(t >> 7), one load each (the
+//         lanes of a wavefront read 64 consecutive rows).
 // Elements outside the operand are zero, except that row `ones` reads 1.
 struct Src {
   const void* p;
@@ -108,15 +114,17 @@ __device__ __forceinline__ void fetch4(const Src& o, int64_t off, float* v) {
   }
 }
 
-template <bool KMAJ, int SRC>
+template <bool KMAJ, int SRC, int KT>
 __device__ __forceinline__ void load_tile(const Src& o, int64_t kend, int64_t r0, int64_t k0,
-                                          float (&v)[16]) {
+                                          float (&v)[KT / 2]) {
+  constexpr int LPR = KT / 4;               // KMAJ: lanes per row, 4 consecutive k each
+  constexpr int RUN = KT / 2;               // else: consecutive k per thread
   const int t = threadIdx.x;
   if constexpr (KMAJ) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int64_t r = r0 + (t >> 3) + 32 * q;
-      const int64_t k = k0 + 4 * (t & 7);
+    for (int q = 0; q < KT / 8; ++q) {
+      const int64_t r = r0 + t / LPR + (kGemmThreads / LPR) * q;
+      const int64_t k = k0 + 4 * (t % LPR);
       if (o.vec && r < o.rows && k + 3 < kend) {
         fetch4<SRC>(o, r * o.ld + k, v + 4 * q);
       } else {
@@ -127,19 +135,19 @@ __device__ __forceinline__ void load_tile(const Src& o, int64_t kend, int64_t r0
     }
   } else {
     const int64_t r = r0 + (t & 127);
-    const int64_t k = k0 + 16 * (t >> 7);
+    const int64_t k = k0 + RUN * (t >> 7);
     const bool rv = r < o.rows;
     const float outside = r == o.ones ? 1.f : 0.f;
     int64_t off = k * o.ld + r;
-    if (rv && k + 16 <= kend) {               // the whole run is inside the operand
+    if (rv && k + RUN <= kend) {              // the whole run is inside the operand
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
+      for (int j = 0; j < RUN; ++j) {
         v[j] = fetch1<SRC>(o, off);
         off += o.ld;
       }
     } else {
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
+      for (int j = 0; j < RUN; ++j) {
         v[j] = (k + j < kend) ? (rv ? fetch1<SRC>(o, off) : outside) : 0.f;
         off += o.ld;
       }
@@ -149,7 +157,8 @@ __device__ __forceinline__ void load_tile(const Src& o, int64_t kend, int64_t r0
 
 // The tile in LDS as [128 rows][PITCH], k contiguous, in the compute type (the conversion to
 // bf16 is the nearest-even rounding of the operand).  Rows are 16-byte aligned: the KMAJ
-// runs go out as one 8-byte (bf16) or 16-byte (fp32) store, the 16-k runs as 16-byte stores.
+// runs go out as one 8-byte (bf16) or 16-byte (fp32) store, the KT/2-k runs as 16-byte
+// stores.
 template <typename LT>
 __device__ __forceinline__ void put(LT* dst, const float* x, int n) {
   if constexpr (std::is_same<LT, float>::value) {
@@ -164,27 +173,34 @@ __device__ __forceinline__ void put(LT* dst, const float* x, int n) {
   }
 }
 
-template <bool KMAJ, typename LT, int PITCH>
-__device__ __forceinline__ void store_tile(LT* __restrict__ lds, const float (&v)[16]) {
+template <bool KMAJ, typename LT, int PITCH, int KT>
+__device__ __forceinline__ void store_tile(LT* __restrict__ lds, const float (&v)[KT / 2]) {
+  constexpr int LPR = KT / 4, RUN = KT / 2;
   const int t = threadIdx.x;
   if constexpr (KMAJ) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) put<LT>(lds + ((t >> 3) + 32 * q) * PITCH + 4 * (t & 7), v + 4 * q, 4);
+    for (int q = 0; q < KT / 8; ++q)
+      put<LT>(lds + (t / LPR + (kGemmThreads / LPR) * q) * PITCH + 4 * (t % LPR), v + 4 * q, 4);
   } else {
-    put<LT>(lds + (t & 127) * PITCH + 16 * (t >> 7), v, 16);
+    put<LT>(lds + (t & 127) * PITCH + RUN * (t >> 7), v, RUN);
   }
 }
 
 template <bool BF, bool AK, bool BK, int EPI, int ASRC>
 __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(GemmArgs g) {
   using LT = typename std::conditional<BF, __bf16, float>::type;
+  constexpr int KT = k_tile(BF, AK, BK);
   // rows of 16-byte multiples, padded against bank conflicts of the fragment reads
-  constexpr int PITCH = BF ? kBK + 8 : kBK + 4;
+  constexpr int PITCH = BF ? KT + 8 : KT + 4;
   constexpr int TILE = kBM * PITCH;
   __shared__ __attribute__((aligned(16))) LT As[2 * TILE];   // two buffers: one barrier
   __shared__ __attribute__((aligned(16))) LT Bs[2 * TILE];   // per k-tile
 
-  const int64_t tile = blockIdx.x;
+  // Blocks go to the 8 XCDs round-robin (block b to XCD b mod 8), each with its own L2.
+  // Give each XCD a contiguous run of tiles: the tiles that share an A row block (same m,
+  // consecutive n) then meet in one L2 instead of fetching it once per XCD.
+  const int64_t nb = (int64_t)gridDim.x, b = blockIdx.x, per = nb / kXcds;
+  const int64_t tile = b < per * kXcds ? (b % kXcds) * per + b / kXcds : b;
   const int64_t n0 = (tile % g.n_tiles) * kBN;
   const int64_t m0 = (tile / g.n_tiles) * kBM;
   const int64_t kb = (int64_t)blockIdx.z * g.k_split;
@@ -202,27 +218,27 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(GemmArgs g) {
 
   const Src sa{g.A, g.lda, g.M, -1, g.vec_a};
   const Src sb{g.B, g.ldb, g.ones_col >= 0 ? g.ones_col : g.N, g.ones_col, g.vec_b};
-  float va[16], vb[16];
+  float va[KT / 2], vb[KT / 2];
   int cur = 0;
   if (kb < ke) {
-    load_tile<AK, ASRC>(sa, ke, m0, kb, va);
-    load_tile<BK, kPlain>(sb, ke, n0, kb, vb);
-    store_tile<AK, LT, PITCH>(As, va);
-    store_tile<BK, LT, PITCH>(Bs, vb);
+    load_tile<AK, ASRC, KT>(sa, ke, m0, kb, va);
+    load_tile<BK, kPlain, KT>(sb, ke, n0, kb, vb);
+    store_tile<AK, LT, PITCH, KT>(As, va);
+    store_tile<BK, LT, PITCH, KT>(Bs, vb);
   }
   __syncthreads();
-  for (int64_t k0 = kb; k0 < ke; k0 += kBK) {
-    const bool more = k0 + kBK < ke;
+  for (int64_t k0 = kb; k0 < ke; k0 += KT) {
+    const bool more = k0 + KT < ke;
     if (more) {                          // next k-tile's loads overlap this tile's MFMAs
-      load_tile<AK, ASRC>(sa, ke, m0, k0 + kBK, va);
-      load_tile<BK, kPlain>(sb, ke, n0, k0 + kBK, vb);
+      load_tile<AK, ASRC, KT>(sa, ke, m0, k0 + KT, va);
+      load_tile<BK, kPlain, KT>(sb, ke, n0, k0 + KT, vb);
     }
     const LT* Ac = As + cur * TILE;
     const LT* Bc = Bs + cur * TILE;
     if constexpr (BF) {
       // fragment: lane holds row rl, k = 16 s + 8 kg .. +8 (A: rows m, B: rows n of Bs)
 #pragma unroll
-      for (int s = 0; s < kBK / 16; ++s) {
+      for (int s = 0; s < KT / 16; ++s) {
         bf16x8 a[2], b[2];
 #pragma unroll
         for (int i = 0; i < 2; ++i)
@@ -241,7 +257,7 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(GemmArgs g) {
     } else {
       // fragment: lane holds row rl, k = 2 s + kg
 #pragma unroll
-      for (int s = 0; s < kBK / 2; ++s) {
+      for (int s = 0; s < KT / 2; ++s) {
         float a[2], b[2];
 #pragma unroll
         for (int i = 0; i < 2; ++i) a[i] = Ac[(64 * wm + 32 * i + rl) * PITCH + 2 * s + kg];
@@ -255,8 +271,8 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(GemmArgs g) {
       }
     }
     if (more) {                          // the other buffer was last read before the
-      store_tile<AK, LT, PITCH>(As + (cur ^ 1) * TILE, va);   // previous barrier
-      store_tile<BK, LT, PITCH>(Bs + (cur ^ 1) * TILE, vb);
+      store_tile<AK, LT, PITCH, KT>(As + (cur ^ 1) * TILE, va);   // previous barrier
+      store_tile<BK, LT, PITCH, KT>(Bs + (cur ^ 1) * TILE, vb);
     }
     __syncthreads();
     cur ^= 1;
@@ -397,8 +413,9 @@ size_t round256(size_t b) { return (b + 255) & ~(size_t)255; }
 // Slices of the weight-gradient reduction over the M batch rows: none while the output
 // tiles (N rows by `cols` columns) alone give a block per compute unit, else enough for
 // about two blocks per unit, each slice at least 512 rows long.  *k_split: rows per slice
-// (a multiple of the k-tile).
-int dense_wgrad_splits(int64_t M, int N, int cols, int64_t* k_split) {
+// (a multiple of the compute type's k-tile).
+int dense_wgrad_splits(int64_t M, int N, int cols, bool bf16, int64_t* k_split) {
+  const int kt = k_tile(bf16, false, false);
   const int64_t tiles = (int64_t)((N + kBM - 1) / kBM) * ((cols + kBN - 1) / kBN);
   int64_t S = 1;
   if (tiles < 256) {
@@ -407,8 +424,8 @@ int dense_wgrad_splits(int64_t M, int N, int cols, int64_t* k_split) {
     if (S > cap) S = cap;
   }
   int64_t ks = (M + S - 1) / S;
-  ks = (ks + kBK - 1) / kBK * kBK;
-  if (ks < kBK) ks = kBK;
+  ks = (ks + kt - 1) / kt * kt;
+  if (ks < kt) ks = kt;
   S = (M + ks - 1) / ks;
   if (S < 1) S = 1;
   if (k_split) *k_split = ks;
@@ -419,7 +436,7 @@ int dense_wgrad_splits(int64_t M, int N, int cols, int64_t* k_split) {
 // reduction's partials.
 size_t dense_bwd_workspace_bytes(int64_t M, int N, int K, bool bias, bool relu, bool bf16) {
   const int cols = K + (bias ? 1 : 0);
-  const int S = dense_wgrad_splits(M, N, cols, nullptr);
+  const int S = dense_wgrad_splits(M, N, cols, bf16, nullptr);
   const size_t da = relu ? round256((size_t)M * N * (bf16 ? 2 : 4)) : 0;
   const size_t part = S > 1 ? round256((size_t)S * N * cols * sizeof(float)) : 0;
   return da + part > 0 ? da + part : 256;
@@ -441,7 +458,8 @@ hipError_t launch_dense_fwd(const float* X, int64_t xs, int64_t M, int K, const 
   g.ldc = ys;
   g.bias = b;
   g.relu = relu;
-  g.k_split = ((int64_t)K + kBK - 1) / kBK * kBK;
+  const int kt = k_tile(bf16, true, true);
+  g.k_split = ((int64_t)K + kt - 1) / kt * kt;
   g.vec_a = vec_ok(X, xs, 4);
   g.vec_b = vec_ok(W, K, 4);
   g.ones_col = -1;
@@ -499,7 +517,8 @@ hipError_t launch_dense_bwd_sgd(const float* X, int64_t xs, int64_t M, int K, fl
     g.K = N;
     g.C = dX;
     g.ldc = dxs;
-    g.k_split = ((int64_t)N + kBK - 1) / kBK * kBK;
+    const int kt = k_tile(bf16, true, false);
+    g.k_split = ((int64_t)N + kt - 1) / kt * kt;
     g.vec_a = vec_ok(dA, lda, a_bf16 ? 2 : 4);
     g.vec_b = vec_ok(W, K, 4);
     g.ones_col = -1;
@@ -510,7 +529,7 @@ hipError_t launch_dense_bwd_sgd(const float* X, int64_t xs, int64_t M, int K, fl
   //    the bias column K, reduced over the m rows (A[n, m] = dA[m, n], B[m, k] = X[m, k])
   const int cols = K + (b ? 1 : 0);
   int64_t ks = 0;
-  const int S = dense_wgrad_splits(M, N, cols, &ks);
+  const int S = dense_wgrad_splits(M, N, cols, bf16, &ks);
   GemmArgs g{};
   g.A = dA;
   g.lda = lda;
