@@ -360,14 +360,29 @@ __global__ __launch_bounds__(kHeadThreads) void logistic_ne_kernel(
   const int t = threadIdx.x;
   const float fm = (float)M;
   float ce = 0.f, ys = 0.f;
-  for (int64_t i = t; i < M; i += kHeadThreads) {
-    const float x = s[i * ss], l = y[i];
-    const float e = expf(-fabsf(x));
-    const float p = x >= 0.f ? 1.f / (1.f + e) : e / (1.f + e);
-    ce += (fmaxf(x, 0.f) - l * x) + log1pf(e);
-    ys += l;
-    if (prob) prob[i] = p;
-    if (dl) dl[i * dls] = (p - l) / fm;
+  // four elements per thread per round, all loads issued before any is used
+  constexpr int U = 4;
+  for (int64_t i0 = t; i0 < M; i0 += (int64_t)U * kHeadThreads) {
+    float xs[U], ls[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t i = i0 + (int64_t)u * kHeadThreads;
+      const int64_t ic = i < M ? i : M - 1;
+      xs[u] = s[ic * ss];
+      ls[u] = y[ic];
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t i = i0 + (int64_t)u * kHeadThreads;
+      if (i >= M) break;
+      const float x = xs[u], l = ls[u];
+      const float e = expf(-fabsf(x));
+      const float p = x >= 0.f ? 1.f / (1.f + e) : e / (1.f + e);
+      ce += (fmaxf(x, 0.f) - l * x) + log1pf(e);
+      ys += l;
+      if (prob) prob[i] = p;
+      if (dl) dl[i * dls] = (p - l) / fm;
+    }
   }
   red_ce[t] = ce;
   red_y[t] = ys;
