@@ -505,7 +505,8 @@ int32_t ctr_step_run_deep(const ctr_step_t* step, int64_t k, void* main_stream,
  * W: fp32 [N, K] contiguous; b: fp32 [N] or NULL (no bias); Y: fp32 rows of stride y_stride
  * (>= N; e.g. Z[:, 0, :] of the interaction input with y_stride = F * dim).
  * compute: CTR_F32 (fp32 products and sums) or CTR_BF16 (X and W rounded to bf16
- * nearest-even, fp32 accumulation).  1 <= K, N <= 65536.  M = 0 is a no-op.
+ * nearest-even, fp32 accumulation).  1 <= K, N <= 65536; M * N, M * K and N * (K + 1) below
+ * 2^31.  Y must not overlap X, W or b.  M = 0 is a no-op.
  */
 int32_t ctr_dense_fwd(const float* X, int64_t x_stride, int64_t M, int32_t K, const float* W,
                       const float* b, int32_t N, int32_t relu, int32_t compute, float* Y,
@@ -522,8 +523,9 @@ int32_t ctr_dense_fwd(const float* X, int64_t x_stride, int64_t M, int32_t K, co
  * constant input 1, so its gradient is the same product (rounded dA times 1).  dA is never
  * stored: it is formed from dY and Y as the GEMMs load it.  The weight-gradient reduction
  * may be split over the rows into partials summed in a fixed order: results are
- * deterministic.  workspace: two-call query (the partials, S * N * (K + 1) floats when the
- * reduction is split; a small constant otherwise).  M = 0 is a no-op (W and b unchanged).
+ * deterministic.  workspace: two-call query (dA for a ReLU layer, M * N in the compute type;
+ * the partials, S * N * (K + 1) floats, when the reduction is split).  dX must not overlap
+ * the other arrays.  Sizes as for ctr_dense_fwd.  M = 0 is a no-op (W and b unchanged).
  */
 int32_t ctr_dense_bwd_sgd(const float* X, int64_t x_stride, int64_t M, int32_t K, float* W,
                           float* b, int32_t N, int32_t relu, const float* Y, int64_t y_stride,

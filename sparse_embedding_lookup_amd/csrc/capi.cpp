@@ -586,8 +586,10 @@ static int32_t check_dense(int64_t M, int32_t K, int32_t N, int32_t compute, int
     return fail(CTR_ERR_INVALID_ARGUMENT, "compute %d is not CTR_F32 or CTR_BF16", compute);
   if (x_stride < K) return fail(CTR_ERR_INVALID_ARGUMENT, "x_stride < K");
   if (y_stride < N) return fail(CTR_ERR_INVALID_ARGUMENT, "y_stride < N");
-  if (M * (int64_t)N > kMaxElems * 64 || M * (int64_t)K > kMaxElems * 64)
-    return fail(CTR_ERR_INVALID_ARGUMENT, "M * N and M * K must be below 2^37");
+  // one work-item per element in the elementwise passes: keep every product below 2^31
+  if (M * (int64_t)N > kMaxElems || M * (int64_t)K > kMaxElems ||
+      (int64_t)N * (K + 1) > kMaxElems)
+    return fail(CTR_ERR_INVALID_ARGUMENT, "M * N, M * K and N * (K + 1) must be below 2^31");
   return CTR_OK;
 }
 

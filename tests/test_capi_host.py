@@ -287,6 +287,7 @@ def test_dense_and_head_bad_args():
     assert f(ys=3) == ctr.CTR_ERR_INVALID_ARGUMENT
     assert f(W=None) == ctr.CTR_ERR_INVALID_ARGUMENT
     assert f(M=-1) == ctr.CTR_ERR_INVALID_ARGUMENT
+    assert f(M=1 << 22, N=1024, ys=1024) == ctr.CTR_ERR_INVALID_ARGUMENT       # M * N >= 2^31
     # backward: workspace query, then a too-small and a misaligned workspace
     wsb = ctypes.c_size_t(0)
     assert lib.ctr_dense_bwd_sgd(None, 13, 10, 13, None, None, 4, 1, None, 4, None, 0, 4, 0,
