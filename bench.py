@@ -150,6 +150,42 @@ class TimingEvent:
         return ms.value
 
 
+def cpu_baseline_variants(fe, w, seconds: float):
+    """The oracle's interaction variants (self-dot pairs and the FM sum, forward and
+    backward) on the first samples of the workload's Z, repeated until `seconds` in total;
+    samples per second for each call."""
+    import numpy as np
+    from oracle import oracle as orc
+
+    B, F, d = w.batch, w.F, w.dim
+    P = F * (F + 1) // 2
+    rng = np.random.default_rng(9)
+    Zs = fe.Z[:min(B, 4096)].double().cpu().numpy()
+    dR = rng.standard_normal((Zs.shape[0], d + P))
+    dout = rng.standard_normal(Zs.shape[0])
+    calls = {"interaction_self_fwd": lambda z, r, o: orc.interaction_self_fwd(z),
+             "interaction_self_bwd": lambda z, r, o: orc.interaction_self_bwd(z, r),
+             "fm_fwd": lambda z, r, o: orc.fm_fwd(z),
+             "fm_bwd": lambda z, r, o: orc.fm_bwd(z, o)}
+    res = {}
+    for name, fn in calls.items():
+        t0 = time.perf_counter()                  # size the sample from a 64-sample call
+        fn(Zs[:64], dR[:64], dout[:64])
+        t1 = time.perf_counter() - t0
+        b = int(min(Zs.shape[0], max(64, 64 * seconds / 4 / max(t1, 1e-6))))
+        reps = 0
+        t0 = time.perf_counter()
+        while True:
+            fn(Zs[:b], dR[:b], dout[:b])
+            reps += 1
+            el = time.perf_counter() - t0
+            if el >= seconds / 4 or reps >= 100:
+                break
+        res[name] = {"value": reps * b / el, "unit": "samples/s", "cores": orc.get_threads(),
+                     "kind": "oracle", "sample": "%d call(s) on the first %d samples" % (reps, b)}
+    return res
+
+
 def time_variants(fe, w, K: int):
     """The interaction variants on the workload's Z (after the timed steps), each call alone
     bracketed by HIP events: the pair set with self-dots, forward and backward (P = F(F+1)/2),
@@ -761,6 +797,12 @@ def main():
         ms_serial = (time.perf_counter() - t2) * 1e3 / K
 
     variants = time_variants(fe, w, K) if (w.interaction and args.variants) else None
+    if variants is not None and not args.no_cpu:
+        print("[bench] CPU oracle of the interaction variants", file=sys.stderr, flush=True)
+        cb = cpu_baseline_variants(fe, w, min(args.cpu_seconds, 8.0))
+        for name, v in cb.items():
+            variants[name]["cpu_baseline"] = v
+            variants[name]["samples_per_s"] = w.batch / (variants[name]["ms"] * 1e-3)
     dlrm = None
     if w.interaction and args.dlrm:
         print("[bench] timing the whole DLRM step", file=sys.stderr, flush=True)
