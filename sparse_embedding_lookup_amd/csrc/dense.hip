@@ -427,16 +427,24 @@ size_t round256(size_t b) { return (b + 255) & ~(size_t)255; }
 
 // Slices of the weight-gradient reduction over the M batch rows: none while the output
 // tiles (N rows by `cols` columns) alone give a block per compute unit, else enough for
-// about two blocks per unit, each slice at least 512 rows long.  *k_split: rows per slice
+// about two blocks per unit (six when slices would be 4096 rows or longer), each slice at
+// least 512 rows long.  *k_split: rows per slice
 // (a multiple of the compute type's k-tile).
 int dense_wgrad_splits(int64_t M, int N, int cols, bool bf16, int64_t* k_split) {
   const int kt = k_tile(bf16, false, false);
   const int64_t tiles = (int64_t)((N + kBM - 1) / kBM) * ((cols + kBN - 1) / kBN);
   int64_t S = 1;
   if (tiles < 256) {
-    S = (512 + tiles - 1) / tiles;
     const int64_t cap = M / 512 > 1 ? M / 512 : 1;
+    S = (512 + tiles - 1) / tiles;
     if (S > cap) S = cap;
+    // long slices: aim for about six blocks per unit instead, so that the last blocks of
+    // the grid do not leave units idle for a whole long slice (a 32768 x 2208 -> 1024
+    // layer's weight GEMM went from 0.97 to 0.72 ms; shorter slices gain nothing)
+    if (M / S >= 4096) {
+      S = (1536 + tiles - 1) / tiles;
+      if (S > cap) S = cap;
+    }
   }
   int64_t ks = (M + S - 1) / S;
   ks = (ks + kt - 1) / kt * kt;
