@@ -207,11 +207,18 @@ def _fwd_case(name):
         off = np.array([0, 200_000], dtype=np.int64)
         ids = rng.integers(0, rows[0], size=200_000)
         return rows, 16, "f32", ids, off, 1, 1
+    if name == "one_bag_1m_d4":
+        # a single bag of 10^6 occurrences: every lane group of every block of the grid
+        # shares one bag
+        rows = [100_000]
+        off = np.array([0, 1_000_000], dtype=np.int64)
+        ids = rng.integers(0, rows[0], size=1_000_000)
+        return rows, 4, "f32", ids, off, 1, 1
     raise KeyError(name)
 
 
 FWD_CASES = ["tiny", "small_b512", "criteo_b512", "empty_bags_d4", "bf16_d8_long", "f32_d512",
-             "mixed_tables_d64", "one_bag_200k"]
+             "mixed_tables_d64", "one_bag_200k", "one_bag_1m_d4"]
 
 
 @pytest.mark.parametrize("name", FWD_CASES)
@@ -308,6 +315,11 @@ def _bwd_case(name):
         rows = [10]
         B = 150_001
         return rows, 16, np.full(B, 3, np.int64), np.arange(B + 1, dtype=np.int64), B, 1
+    if name == "one_key_1m_d4":
+        # one segment of 10^6 occurrences (the hottest-key limit)
+        rows = [10]
+        B = 1_000_000
+        return rows, 4, np.full(B, 3, np.int64), np.arange(B + 1, dtype=np.int64), B, 1
     if name == "empty_bags_d4":
         rows = [50, 70]
         ids, off = rand_csr(rng, 2, 401, rows, 9, empty_frac=0.25)
@@ -320,7 +332,7 @@ def _bwd_case(name):
 
 
 BWD_CASES = ["tiny", "small_b512", "criteo_b256", "hot_segment_d32", "all_one_key_d16",
-             "empty_bags_d4", "d512"]
+             "one_key_1m_d4", "empty_bags_d4", "d512"]
 
 
 @pytest.mark.parametrize("name", BWD_CASES)
