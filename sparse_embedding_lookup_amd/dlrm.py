@@ -12,8 +12,11 @@ Forward   bottom layers (ReLU each; the last writes Z[:, 0, :]), pooled bags int
           Z[:, 1:, :], the interaction -> R, top layers (ReLU, then a linear logit), the head
           (sigmoid, cross-entropy sums, NE, d logit).
 Backward  top layers in reverse (each updates its W, b by SGD; the first writes dR), the
-          interaction backward -> dZ, the batch's unique, the fused embedding backward with
-          the sparse SGD step, bottom layers in reverse (dZ[:, 0, :] feeds the last).
+          interaction backward -> dZ, the fused embedding backward with the sparse SGD step,
+          bottom layers in reverse (dZ[:, 0, :] feeds the last).
+The batch's unique needs only its IDs: with overlap=True it runs on a side stream from the
+step's start (after everything before the step) and is joined just before the embedding
+backward, so it overlaps the forward, the top MLP's backward and the interaction's.
 Nothing here computes: torch allocates, and every step is a C-ABI call marshalled once.
 """
 from __future__ import annotations
@@ -44,10 +47,13 @@ class DlrmStep:
     bf16 operands with fp32 accumulation)."""
 
     def __init__(self, w: Workload, inputs: DlrmInputs, device="cuda",
-                 table: Optional[torch.Tensor] = None, lr: Optional[float] = None):
+                 table: Optional[torch.Tensor] = None, lr: Optional[float] = None,
+                 overlap: bool = True):
         assert w.interaction, "the DLRM step needs the pooled-interaction workload"
         self.w = w
         self.device = torch.device(device)
+        self.overlap = overlap
+        self.side = torch.cuda.Stream(device=self.device) if overlap else None
         self.fe = FrontEnd(w, device, table=table)
         self.lr = float(w.lr if lr is None else lr)
         self.compute = self.fe.compute
@@ -108,17 +114,30 @@ class DlrmStep:
         self._head()
 
     def backward(self):
+        """Everything after the head; the batch's unique must already be enqueued (step()
+        does that)."""
         for call in reversed(self._bwd_top):
             call()
         fe = self.fe
         fe._interaction_bwd()
-        fe.unique()
+        if self.overlap:
+            torch.cuda.current_stream(self.device).wait_stream(self.side)
         fe._embbag_bwd_sgd()
         for call in reversed(self._bwd_bottom):
             call()
 
     def step(self):
         """One training step: forward, head, backward with every SGD update."""
+        fe = self.fe
+        if self.overlap:
+            # the unique of this batch on the side stream, after everything enqueued so far
+            # (so after the previous step's backward, which read the unique outputs)
+            main = torch.cuda.current_stream(self.device)
+            self.side.wait_stream(main)
+            with torch.cuda.stream(self.side):
+                fe.unique()
+        else:
+            fe.unique()
         self.forward()
         self.backward()
 

@@ -144,3 +144,25 @@ def test_dlrm_training_lowers_the_loss():
         s.step()
     last = float(host(s.stats)[0])
     assert last < 0.9 * first, (first, last)
+
+
+@pytest.mark.parametrize("graph", [False, True])
+def test_dlrm_overlapped_unique_matches_serial(graph):
+    """The unique on a side stream (overlap=True) gives the same bits as running it in line,
+    step after step, eager or replayed from a graph."""
+    w = workloads.criteo(batch=128)
+    inp = workloads.dlrm_inputs(w, seed=4)
+    a = DlrmStep(w, inp, DEV, overlap=False)
+    b = DlrmStep(w, inp, DEV, overlap=True)
+    g = b.capture(steps=1) if graph else None
+    for k in range(3):
+        a.step()
+        if graph:
+            g.replay()
+        else:
+            b.step()
+        torch.cuda.synchronize()
+        for pa, pb in zip(a.parameters(), b.parameters()):
+            assert torch.equal(pa, pb), k
+        assert torch.equal(a.fe.table, b.fe.table), k
+        assert torch.equal(a.stats, b.stats), k
