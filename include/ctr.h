@@ -523,9 +523,11 @@ int32_t ctr_dense_fwd(const float* X, int64_t x_stride, int64_t M, int32_t K, co
  * constant input 1, so its gradient is the same product (rounded dA times 1).  dA is never
  * stored: it is formed from dY and Y as the GEMMs load it.  The weight-gradient reduction
  * may be split over the rows into partials summed in a fixed order: results are
- * deterministic.  workspace: two-call query (dA for a ReLU layer, M * N in the compute type;
- * the partials, S * N * (K + 1) floats, when the reduction is split).  dX must not overlap
- * the other arrays.  Sizes as for ctr_dense_fwd.  M = 0 is a no-op (W and b unchanged).
+ * deterministic; so may dX's reduction over the N outputs when its grid is small.
+ * workspace: two-call query (dA for a ReLU layer, M * N in the compute type; the weight
+ * gradient's partials, S * N * (K + 1) floats, and dX's, S' * M * K floats, when those
+ * reductions are split).  dX must not overlap the other arrays.  Sizes as for
+ * ctr_dense_fwd.  M = 0 is a no-op (W and b unchanged).
  */
 int32_t ctr_dense_bwd_sgd(const float* X, int64_t x_stride, int64_t M, int32_t K, float* W,
                           float* b, int32_t N, int32_t relu, const float* Y, int64_t y_stride,

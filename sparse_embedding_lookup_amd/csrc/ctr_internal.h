@@ -175,6 +175,7 @@ hipError_t launch_fm_bwd(const float* Z, const float* dout, int64_t batch, int F
 
 // dense.hip: fully connected layers and the logistic head
 int dense_wgrad_splits(int64_t M, int N, int cols, bool bf16, int64_t* k_split);
+int dense_dx_splits(int64_t M, int N, int K, int64_t* k_split);
 size_t dense_bwd_workspace_bytes(int64_t M, int N, int K, bool bias, bool relu, bool bf16);
 hipError_t launch_dense_fwd(const float* X, int64_t xs, int64_t M, int K, const float* W,
                             const float* b, int N, bool relu, bool bf16, float* Y, int64_t ys,

@@ -293,7 +293,10 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(GemmArgs g) {
         if (m >= g.M) continue;
         float x = acc[i][j][v];
         if constexpr (EPI == kStore) {
-          g.C[m * g.ldc + n] = x;
+          if (gridDim.z > 1)             // a slice of a split reduction: its partial sum
+            g.C[((int64_t)blockIdx.z * g.M + m) * g.ldc + n] = x;
+          else
+            g.C[m * g.ldc + n] = x;
         } else if constexpr (EPI == kBiasAct) {
           x += bn;
           if (g.relu) x = x > 0.f ? x : 0.f;
@@ -324,6 +327,20 @@ __global__ __launch_bounds__(256) void sgd_from_partials_kernel(
   const int64_t n = i / cols, c = i - n * cols;
   float* t = c < K ? W + n * K + c : b + n;
   *t = __builtin_fmaf(-lr, s, *t);
+}
+
+// dX from the split dX reduction: part[s] is [M, K]; dX[m * dxs + k] = the sum over the S
+// slices, in order.
+__global__ __launch_bounds__(256) void sum_slices_kernel(const float* __restrict__ part,
+                                                         int64_t M, int64_t K, int S,
+                                                         float* __restrict__ dX, int64_t dxs) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t count = M * K;
+  if (i >= count) return;
+  float s = 0.f;
+  for (int z = 0; z < S; ++z) s += part[z * count + i];
+  const int64_t m = i / K, k = i - m * K;
+  dX[m * dxs + k] = s;
 }
 
 // dA[m, n] = dY[m, n] * [Y[m, n] > 0], contiguous [M, N], fp32 or bf16 nearest-even (OUTB).
@@ -428,14 +445,14 @@ size_t round256(size_t b) { return (b + 255) & ~(size_t)255; }
 // Slices of the weight-gradient reduction over the M batch rows: none while the output
 // tiles (N rows by `cols` columns) alone give a block per compute unit, else enough for
 // about two blocks per unit (six when slices would be 4096 rows or longer), each slice at
-// least 512 rows long.  *k_split: rows per slice
+// least 128 rows long.  *k_split: rows per slice
 // (a multiple of the compute type's k-tile).
 int dense_wgrad_splits(int64_t M, int N, int cols, bool bf16, int64_t* k_split) {
   const int kt = k_tile(bf16, false, false);
   const int64_t tiles = (int64_t)((N + kBM - 1) / kBM) * ((cols + kBN - 1) / kBN);
   int64_t S = 1;
   if (tiles < 256) {
-    const int64_t cap = M / 512 > 1 ? M / 512 : 1;
+    const int64_t cap = M / 128 > 1 ? M / 128 : 1;
     S = (512 + tiles - 1) / tiles;
     if (S > cap) S = cap;
     // long slices: aim for about six blocks per unit instead, so that the last blocks of
@@ -457,12 +474,37 @@ int dense_wgrad_splits(int64_t M, int N, int cols, bool bf16, int64_t* k_split) 
 
 // Workspace of the backward: dA (ReLU layers: M * N in the compute type), then the split
 // reduction's partials.
+// Slices of dX's reduction over the layer's N outputs when its output tiles (M rows by K
+// columns) alone are too few to fill the chip: about two blocks per unit, each slice at
+// least 128 outputs long.  *k_split: outputs per slice (a multiple of the k-tile).
+int dense_dx_splits(int64_t M, int N, int K, int64_t* k_split) {
+  const int kt = k_tile(false, true, false);
+  const int64_t tiles = ((M + kBM - 1) / kBM) * (int64_t)((K + kBN - 1) / kBN);
+  int64_t S = 1;
+  if (tiles > 0 && tiles < 256) {      // M = 0: no tiles, nothing to split
+    const int64_t cap = N / 128 > 1 ? N / 128 : 1;
+    S = (512 + tiles - 1) / tiles;
+    if (S > cap) S = cap;
+  }
+  int64_t ks = (N + S - 1) / S;
+  ks = (ks + kt - 1) / kt * kt;
+  if (ks < kt) ks = kt;
+  S = (N + ks - 1) / ks;
+  if (S < 1) S = 1;
+  if (k_split) *k_split = ks;
+  return (int)S;
+}
+
+// The backward's workspace: dA (ReLU layers), then the weight gradient's partials, then dX's
+// (both only when their reductions are split; dX's counted whether or not dX is asked for).
 size_t dense_bwd_workspace_bytes(int64_t M, int N, int K, bool bias, bool relu, bool bf16) {
   const int cols = K + (bias ? 1 : 0);
   const int S = dense_wgrad_splits(M, N, cols, bf16, nullptr);
+  const int Sx = dense_dx_splits(M, N, K, nullptr);
   const size_t da = relu ? round256((size_t)M * N * (bf16 ? 2 : 4)) : 0;
   const size_t part = S > 1 ? round256((size_t)S * N * cols * sizeof(float)) : 0;
-  return da + part > 0 ? da + part : 256;
+  const size_t partx = Sx > 1 ? round256((size_t)Sx * M * K * sizeof(float)) : 0;
+  return da + part + partx > 0 ? da + part + partx : 256;
 }
 
 hipError_t launch_dense_fwd(const float* X, int64_t xs, int64_t M, int K, const float* W,
@@ -528,6 +570,11 @@ hipError_t launch_dense_bwd_sgd(const float* X, int64_t xs, int64_t M, int K, fl
   using F = std::false_type;
   using Store = std::integral_constant<int, kStore>;
   using Sgd = std::integral_constant<int, kSgd>;
+  // the weight gradient's split (its partials follow dA in the workspace, dX's follow those)
+  const int cols = K + (b ? 1 : 0);
+  int64_t ks = 0;
+  const int S = dense_wgrad_splits(M, N, cols, bf16, &ks);
+  const size_t wpart = S > 1 ? round256((size_t)S * N * cols * sizeof(float)) : 0;
   // 2. dX = dA W, with the weights before this step's update (A = dA rows, k = n)
   if (dX) {
     GemmArgs g{};
@@ -538,21 +585,27 @@ hipError_t launch_dense_bwd_sgd(const float* X, int64_t xs, int64_t M, int K, fl
     g.M = M;
     g.N = K;
     g.K = N;
-    g.C = dX;
-    g.ldc = dxs;
-    const int kt = k_tile(bf16, true, false);
-    g.k_split = ((int64_t)N + kt - 1) / kt * kt;
+    int64_t ksx = 0;
+    const int Sx = dense_dx_splits(M, N, K, &ksx);
+    float* partx = reinterpret_cast<float*>(ws + used + wpart);
+    g.C = Sx > 1 ? partx : dX;
+    g.ldc = Sx > 1 ? K : dxs;
+    g.k_split = ksx;
     g.vec_a = vec_ok(dA, lda, a_bf16 ? 2 : 4);
     g.vec_b = vec_ok(W, K, 4);
     g.ones_col = -1;
-    hipError_t e = gemm(T{}, F{}, Store{}, g, 1);
+    hipError_t e = gemm(T{}, F{}, Store{}, g, Sx);
     if (e != hipSuccess) return e;
+    if (Sx > 1) {
+      const int64_t count = M * (int64_t)K;
+      sum_slices_kernel<<<(unsigned)((count + 255) / 256), 256, 0, s>>>(partx, M, K, Sx, dX,
+                                                                        dxs);
+      e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
   }
   // 3. [W | b] -= lr dA^T [X | 1]: rows n of the layer's output, columns k of its input and
   //    the bias column K, reduced over the m rows (A[n, m] = dA[m, n], B[m, k] = X[m, k])
-  const int cols = K + (b ? 1 : 0);
-  int64_t ks = 0;
-  const int S = dense_wgrad_splits(M, N, cols, bf16, &ks);
   GemmArgs g{};
   g.A = dA;
   g.lda = lda;

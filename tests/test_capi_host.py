@@ -294,6 +294,9 @@ def test_dense_and_head_bad_args():
                                  0.1, None, 13, None, ctypes.byref(wsb), None) == ctr.CTR_OK
     assert wsb.value >= 10 * 4 * 4                                    # dA of a ReLU layer
     assert wsb.value == ctr.dense_bwd_workspace_bytes(10, 13, 4, bias=False)
+    # zero rows: a valid query (no tiles to split)
+    assert ctr.dense_bwd_workspace_bytes(0, 13, 4) >= 16
+    assert ctr.dense_bwd_workspace_bytes(0, 2048, 2048, compute=ctr.CTR_BF16) >= 16
     # bf16 compute keeps dA in bf16; a linear layer needs no dA
     assert ctr.dense_bwd_workspace_bytes(1000, 13, 64, compute=ctr.CTR_BF16) < \
         ctr.dense_bwd_workspace_bytes(1000, 13, 64)
