@@ -16,7 +16,8 @@ Backward  top layers in reverse (each updates its W, b by SGD; the first writes 
           bottom layers in reverse (dZ[:, 0, :] feeds the last).
 The batch's unique needs only its IDs: with overlap=True it runs on a side stream from the
 step's start (after everything before the step) and is joined just before the embedding
-backward, so it overlaps the forward, the top MLP's backward and the interaction's.
+backward, so it overlaps the forward, the top MLP's backward and the interaction's.  The
+bottom MLP's backward then takes the side stream beside the embedding backward.
 Nothing here computes: torch allocates, and every step is a C-ABI call marshalled once.
 """
 from __future__ import annotations
@@ -115,16 +116,26 @@ class DlrmStep:
 
     def backward(self):
         """Everything after the head; the batch's unique must already be enqueued (step()
-        does that)."""
+        does that).  With overlap, the bottom MLP's backward (which reads dZ[:, 0, :] only)
+        runs on the side stream beside the embedding backward (dZ[:, 1:, :]) and joins
+        before the step ends."""
         for call in reversed(self._bwd_top):
             call()
         fe = self.fe
         fe._interaction_bwd()
         if self.overlap:
-            torch.cuda.current_stream(self.device).wait_stream(self.side)
-        fe._embbag_bwd_sgd()
-        for call in reversed(self._bwd_bottom):
-            call()
+            main = torch.cuda.current_stream(self.device)
+            main.wait_stream(self.side)                  # the unique is done
+            self.side.wait_stream(main)                  # dZ is written
+            with torch.cuda.stream(self.side):
+                for call in reversed(self._bwd_bottom):
+                    call()
+            fe._embbag_bwd_sgd()
+            main.wait_stream(self.side)
+        else:
+            fe._embbag_bwd_sgd()
+            for call in reversed(self._bwd_bottom):
+                call()
 
     def step(self):
         """One training step: forward, head, backward with every SGD update."""
