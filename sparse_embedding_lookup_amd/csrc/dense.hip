@@ -114,15 +114,16 @@ __device__ __forceinline__ void fetch4(const Src& o, int64_t off, float* v) {
   }
 }
 
-template <bool KMAJ, int SRC, int KT>
+template <bool KMAJ, int SRC, int KT, int ROWS>
 __device__ __forceinline__ void load_tile(const Src& o, int64_t kend, int64_t r0, int64_t k0,
-                                          float (&v)[KT / 2]) {
-  constexpr int LPR = KT / 4;               // KMAJ: lanes per row, 4 consecutive k each
-  constexpr int RUN = KT / 2;               // else: consecutive k per thread
+                                          float (&v)[ROWS * KT / kGemmThreads]) {
+  constexpr int LPR = KT / 4;                       // KMAJ: lanes per row, 4 consecutive k
+  constexpr int GROUPS = kGemmThreads / ROWS;       // else: threads per row
+  constexpr int RUN = KT / GROUPS;                  //   and consecutive k per thread
   const int t = threadIdx.x;
   if constexpr (KMAJ) {
 #pragma unroll
-    for (int q = 0; q < KT / 8; ++q) {
+    for (int q = 0; q < ROWS * LPR / kGemmThreads; ++q) {
       const int64_t r = r0 + t / LPR + (kGemmThreads / LPR) * q;
       const int64_t k = k0 + 4 * (t % LPR);
       if (o.vec && r < o.rows && k + 3 < kend) {
@@ -134,8 +135,8 @@ __device__ __forceinline__ void load_tile(const Src& o, int64_t kend, int64_t r0
       }
     }
   } else {
-    const int64_t r = r0 + (t & 127);
-    const int64_t k = k0 + RUN * (t >> 7);
+    const int64_t r = r0 + (t % ROWS);
+    const int64_t k = k0 + RUN * (t / ROWS);
     const bool rv = r < o.rows;
     const float outside = r == o.ones ? 1.f : 0.f;
     int64_t off = k * o.ld + r;
@@ -155,7 +156,7 @@ __device__ __forceinline__ void load_tile(const Src& o, int64_t kend, int64_t r0
   }
 }
 
-// The tile in LDS as [128 rows][PITCH], k contiguous, in the compute type (the conversion to
+// The tile in LDS as [ROWS][PITCH], k contiguous, in the compute type (the conversion to
 // bf16 is the nearest-even rounding of the operand).  Rows are 16-byte aligned: the KMAJ
 // runs go out as one 8-byte (bf16) or 16-byte (fp32) store, the KT/2-k runs as 16-byte
 // stores.
@@ -173,28 +174,32 @@ __device__ __forceinline__ void put(LT* dst, const float* x, int n) {
   }
 }
 
-template <bool KMAJ, typename LT, int PITCH, int KT>
-__device__ __forceinline__ void store_tile(LT* __restrict__ lds, const float (&v)[KT / 2]) {
-  constexpr int LPR = KT / 4, RUN = KT / 2;
+template <bool KMAJ, typename LT, int PITCH, int KT, int ROWS>
+__device__ __forceinline__ void store_tile(LT* __restrict__ lds,
+                                           const float (&v)[ROWS * KT / kGemmThreads]) {
+  constexpr int LPR = KT / 4, RUN = KT / (kGemmThreads / ROWS);
   const int t = threadIdx.x;
   if constexpr (KMAJ) {
 #pragma unroll
-    for (int q = 0; q < KT / 8; ++q)
+    for (int q = 0; q < ROWS * LPR / kGemmThreads; ++q)
       put<LT>(lds + (t / LPR + (kGemmThreads / LPR) * q) * PITCH + 4 * (t % LPR), v + 4 * q, 4);
   } else {
-    put<LT>(lds + (t & 127) * PITCH + RUN * (t >> 7), v, RUN);
+    put<LT>(lds + (t % ROWS) * PITCH + RUN * (t / ROWS), v, RUN);
   }
 }
 
-template <bool BF, bool AK, bool BK, int EPI, int ASRC>
+// TI: 32-row MFMA tiles per wave along m, so the block tile is (64 TI) x 128.  TI = 1 is for
+// grids that 128-row tiles would leave with fewer blocks than compute units.
+template <bool BF, bool AK, bool BK, int EPI, int ASRC, int TI>
 __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(GemmArgs g) {
   using LT = typename std::conditional<BF, __bf16, float>::type;
   constexpr int KT = k_tile(BF, AK, BK);
+  constexpr int BMT = 64 * TI;
   // rows of 16-byte multiples, padded against bank conflicts of the fragment reads
   constexpr int PITCH = BF ? KT + 8 : KT + 4;
-  constexpr int TILE = kBM * PITCH;
-  __shared__ __attribute__((aligned(16))) LT As[2 * TILE];   // two buffers: one barrier
-  __shared__ __attribute__((aligned(16))) LT Bs[2 * TILE];   // per k-tile
+  constexpr int TILEA = BMT * PITCH, TILEB = kBN * PITCH;
+  __shared__ __attribute__((aligned(16))) LT As[2 * TILEA];  // two buffers: one barrier
+  __shared__ __attribute__((aligned(16))) LT Bs[2 * TILEB];  // per k-tile
 
   // Blocks go to the 8 XCDs round-robin (block b to XCD b mod 8), each with its own L2.
   // Give each XCD a contiguous run of tiles: the tiles that share an A row block (same m,
@@ -202,15 +207,15 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(GemmArgs g) {
   const int64_t nb = (int64_t)gridDim.x, b = blockIdx.x, per = nb / kXcds;
   const int64_t tile = b < per * kXcds ? (b % kXcds) * per + b / kXcds : b;
   const int64_t n0 = (tile % g.n_tiles) * kBN;
-  const int64_t m0 = (tile / g.n_tiles) * kBM;
+  const int64_t m0 = (tile / g.n_tiles) * BMT;
   const int64_t kb = (int64_t)blockIdx.z * g.k_split;
   const int64_t ke = g.K < kb + g.k_split ? g.K : kb + g.k_split;
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int wm = wv >> 1, wn = wv & 1, rl = lane & 31, kg = lane >> 5;
 
-  f32x16 acc[2][2];
+  f32x16 acc[TI][2];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < TI; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
@@ -218,38 +223,38 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(GemmArgs g) {
 
   const Src sa{g.A, g.lda, g.M, -1, g.vec_a};
   const Src sb{g.B, g.ldb, g.ones_col >= 0 ? g.ones_col : g.N, g.ones_col, g.vec_b};
-  float va[KT / 2], vb[KT / 2];
+  float va[BMT * KT / kGemmThreads], vb[kBN * KT / kGemmThreads];
   int cur = 0;
   if (kb < ke) {
-    load_tile<AK, ASRC, KT>(sa, ke, m0, kb, va);
-    load_tile<BK, kPlain, KT>(sb, ke, n0, kb, vb);
-    store_tile<AK, LT, PITCH, KT>(As, va);
-    store_tile<BK, LT, PITCH, KT>(Bs, vb);
+    load_tile<AK, ASRC, KT, BMT>(sa, ke, m0, kb, va);
+    load_tile<BK, kPlain, KT, kBN>(sb, ke, n0, kb, vb);
+    store_tile<AK, LT, PITCH, KT, BMT>(As, va);
+    store_tile<BK, LT, PITCH, KT, kBN>(Bs, vb);
   }
   __syncthreads();
   for (int64_t k0 = kb; k0 < ke; k0 += KT) {
     const bool more = k0 + KT < ke;
     if (more) {                          // next k-tile's loads overlap this tile's MFMAs
-      load_tile<AK, ASRC, KT>(sa, ke, m0, k0 + KT, va);
-      load_tile<BK, kPlain, KT>(sb, ke, n0, k0 + KT, vb);
+      load_tile<AK, ASRC, KT, BMT>(sa, ke, m0, k0 + KT, va);
+      load_tile<BK, kPlain, KT, kBN>(sb, ke, n0, k0 + KT, vb);
     }
-    const LT* Ac = As + cur * TILE;
-    const LT* Bc = Bs + cur * TILE;
+    const LT* Ac = As + cur * TILEA;
+    const LT* Bc = Bs + cur * TILEB;
     if constexpr (BF) {
       // fragment: lane holds row rl, k = 16 s + 8 kg .. +8 (A: rows m, B: rows n of Bs)
 #pragma unroll
       for (int s = 0; s < KT / 16; ++s) {
-        bf16x8 a[2], b[2];
+        bf16x8 a[TI], b[2];
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
-          a[i] = *reinterpret_cast<const bf16x8*>(Ac + (64 * wm + 32 * i + rl) * PITCH +
+        for (int i = 0; i < TI; ++i)
+          a[i] = *reinterpret_cast<const bf16x8*>(Ac + (32 * TI * wm + 32 * i + rl) * PITCH +
                                                   16 * s + 8 * kg);
 #pragma unroll
         for (int j = 0; j < 2; ++j)
           b[j] = *reinterpret_cast<const bf16x8*>(Bc + (64 * wn + 32 * j + rl) * PITCH +
                                                   16 * s + 8 * kg);
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
+        for (int i = 0; i < TI; ++i)
 #pragma unroll
           for (int j = 0; j < 2; ++j)
             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
@@ -258,21 +263,21 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(GemmArgs g) {
       // fragment: lane holds row rl, k = 2 s + kg
 #pragma unroll
       for (int s = 0; s < KT / 2; ++s) {
-        float a[2], b[2];
+        float a[TI], b[2];
 #pragma unroll
-        for (int i = 0; i < 2; ++i) a[i] = Ac[(64 * wm + 32 * i + rl) * PITCH + 2 * s + kg];
+        for (int i = 0; i < TI; ++i) a[i] = Ac[(32 * TI * wm + 32 * i + rl) * PITCH + 2 * s + kg];
 #pragma unroll
         for (int j = 0; j < 2; ++j) b[j] = Bc[(64 * wn + 32 * j + rl) * PITCH + 2 * s + kg];
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
+        for (int i = 0; i < TI; ++i)
 #pragma unroll
           for (int j = 0; j < 2; ++j)
             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[i], b[j], acc[i][j], 0, 0, 0);
       }
     }
     if (more) {                          // the other buffer was last read before the
-      store_tile<AK, LT, PITCH, KT>(As + (cur ^ 1) * TILE, va);   // previous barrier
-      store_tile<BK, LT, PITCH, KT>(Bs + (cur ^ 1) * TILE, vb);
+      store_tile<AK, LT, PITCH, KT, BMT>(As + (cur ^ 1) * TILEA, va);   // previous barrier
+      store_tile<BK, LT, PITCH, KT, kBN>(Bs + (cur ^ 1) * TILEB, vb);
     }
     __syncthreads();
     cur ^= 1;
@@ -280,7 +285,7 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(GemmArgs g) {
 
   // acc[i][j][v] = C[m, n]: m = 8 (v / 4) + 4 kg + v % 4 and n = rl within the 32x32 tile
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < TI; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const int64_t n = n0 + 64 * wn + 32 * j + rl;
@@ -289,7 +294,7 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(GemmArgs g) {
       if constexpr (EPI == kBiasAct) bn = g.bias ? g.bias[n] : 0.f;
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const int64_t m = m0 + 64 * wm + 32 * i + 8 * (v >> 2) + 4 * kg + (v & 3);
+        const int64_t m = m0 + 32 * TI * wm + 32 * i + 8 * (v >> 2) + 4 * kg + (v & 3);
         if (m >= g.M) continue;
         float x = acc[i][j][v];
         if constexpr (EPI == kStore) {
@@ -425,16 +430,28 @@ bool vec_ok(const void* p, int64_t ld, int elem_bytes) {
   return ((uintptr_t)p & (4 * elem_bytes - 1)) == 0 && (ld & 3) == 0;
 }
 
+// 64-row tiles when 128-row ones would leave fewer blocks than compute units (forward and
+// dX; the weight gradient fills the chip by splitting its reduction instead).
 template <bool AK, bool BK, int EPI, int ASRC>
 hipError_t launch_gemm(bool bf16, GemmArgs g, int splits, hipStream_t s) {
   g.n_tiles = (g.N + kBN - 1) / kBN;
   const int64_t tiles = g.n_tiles * ((g.M + kBM - 1) / kBM);
   if (tiles == 0) return hipSuccess;
+  if constexpr (EPI != kSgd) {
+    if (tiles * splits < 256) {
+      const dim3 grid((unsigned)(g.n_tiles * ((g.M + 63) / 64)), 1, (unsigned)splits);
+      if (bf16)
+        gemm_kernel<true, AK, BK, EPI, ASRC, 1><<<grid, kGemmThreads, 0, s>>>(g);
+      else
+        gemm_kernel<false, AK, BK, EPI, ASRC, 1><<<grid, kGemmThreads, 0, s>>>(g);
+      return hipGetLastError();
+    }
+  }
   const dim3 grid((unsigned)tiles, 1, (unsigned)splits);
   if (bf16)
-    gemm_kernel<true, AK, BK, EPI, ASRC><<<grid, kGemmThreads, 0, s>>>(g);
+    gemm_kernel<true, AK, BK, EPI, ASRC, 2><<<grid, kGemmThreads, 0, s>>>(g);
   else
-    gemm_kernel<false, AK, BK, EPI, ASRC><<<grid, kGemmThreads, 0, s>>>(g);
+    gemm_kernel<false, AK, BK, EPI, ASRC, 2><<<grid, kGemmThreads, 0, s>>>(g);
   return hipGetLastError();
 }
 

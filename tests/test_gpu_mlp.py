@@ -5,9 +5,10 @@ through the C ABI, against the oracle ("Meta DLRM", 02: bottom and top MLP, sigm
 Per call on identical inputs, both sides round the same fp32 operands to bf16 (nearest-even)
 when the compute type is bf16, so the only difference left is the fp32 summation order: every
 check uses rtol = 1e-5 against the oracle's sum of |terms|, for both compute types.  Shapes
-span one and several 128x128 output tiles, ragged tails in every dimension, widths that are
-not multiples of 4 (scalar loads), strided rows, a one-unit output, and the split
-weight-gradient reduction.
+span one and many output tiles of both heights (64-row tiles for small grids, 128-row ones
+from 256 tiles on), ragged tails in every dimension, widths that are not multiples of 4
+(scalar loads), strided rows, a one-unit output, and the split reductions of the weight
+gradient and of dX.
 """
 import numpy as np
 import pytest
@@ -34,6 +35,9 @@ FWD_CASES = [
     (64, 100, 33, True, True, BF16, 28, 7),
     (513, 64, 64, True, True, F32, 0, 8 * 64 - 64),     # Y = Z[:, 0, :] of a [513, 8, 64] Z
     (200, 2208, 300, True, True, BF16, 0, 0),
+    # 256 output tiles of 128 x 128: the full-height tiles (smaller grids use 64-row tiles)
+    (4096, 64, 1024, True, True, F32, 0, 0),
+    (4096, 64, 1024, True, True, BF16, 0, 0),
 ]
 
 
@@ -67,7 +71,7 @@ def test_dense_fwd_matches_oracle(M, K, N, relu, bias, compute, xp, yp):
         assert np.all(host(big)[:, N:] == -3.0)          # the padding is not written
 
 
-# (M, K, N, relu, bias, compute, with_dx, dy_bf16): the last three split the weight gradient
+# (M, K, N, relu, bias, compute, with_dx, dy_bf16)
 BWD_CASES = [
     (77, 13, 512, True, True, F32, False, False),
     (300, 479, 256, True, True, BF16, True, False),
@@ -78,6 +82,9 @@ BWD_CASES = [
     (4096, 64, 64, True, True, F32, True, False),
     (1024, 479, 256, True, True, BF16, True, False),
     (3000, 13, 512, True, True, F32, False, False),
+    # dX on 256 full-height tiles (no split); the weight gradient split 32 ways
+    (4096, 1024, 64, True, True, BF16, True, False),
+    (4096, 1024, 64, False, True, F32, True, False),
 ]
 
 
