@@ -55,7 +55,8 @@ class DlrmStep:
         self.device = torch.device(device)
         self.overlap = overlap
         self.side = torch.cuda.Stream(device=self.device) if overlap else None
-        self.fe = FrontEnd(w, device, table=table)
+        # R padded to 16-byte rows: the top MLP's first layer reads it with vector loads
+        self.fe = FrontEnd(w, device, table=table, pad_r=True)
         self.lr = float(w.lr if lr is None else lr)
         self.compute = self.fe.compute
         dv = self.device

@@ -36,7 +36,7 @@ class FrontEnd:
 
     def __init__(self, w: Workload, device="cuda", table: Optional[torch.Tensor] = None,
                  fused: bool = True, keep_grads: bool = False, pipelined: bool = False,
-                 rounding: str = "nearest", sr_seed: int = SR_SEED):
+                 rounding: str = "nearest", sr_seed: int = SR_SEED, pad_r: bool = False):
         """fused: the backward applies the sparse SGD as each row gradient completes
         (ctr_embbag_bwd_sgd); otherwise ctr_embbag_bwd then ctr_sparse_sgd.  keep_grads: also
         keep the per-row gradients in self.row_grads (always kept when not fused).
@@ -44,7 +44,10 @@ class FrontEnd:
         deduplicate the next batch's IDs while the current batch trains.
         rounding: "nearest", or "stochastic" (bf16 tables): the k-th update of the run (the
         native step k, or the k-th SGD stage run from Python) draws its rounding bits with
-        seed ctr_sr_step_seed(sr_seed, k)."""
+        seed ctr_sr_step_seed(sr_seed, k).
+        pad_r: R's rows start on 16-byte boundaries (stride rounded up to 4 floats), so that a
+        layer reading R loads it with vector loads; R is then a strided view (the native step
+        runner, which assumes contiguous R, refuses it)."""
         assert rounding in ("nearest", "stochastic")
         assert rounding == "nearest" or w.dtype == "bf16", "stochastic rounding: bf16 tables"
         self.rounding = rounding
@@ -71,7 +74,11 @@ class FrontEnd:
             F = w.F
             self.Z = torch.empty((B, F, d), dtype=torch.float32, device=self.device)
             self.Z[:, 0, :].copy_(_dev(w.dense, self.device))        # batch upload
-            self.R = torch.empty((B, d + w.P), dtype=torch.float32, device=self.device)
+            width = d + w.P
+            stride = (width + 3) // 4 * 4 if pad_r else width
+            self.R = torch.empty((B, stride), dtype=torch.float32,
+                                 device=self.device)[:, :width]
+            self.pad_r = pad_r and stride != width
             self.dR = _dev(w.grad_out, self.device)
             # a bf16 interaction keeps its gradient in bf16 (the backward re-reads it per
             # occurrence and sums in fp32)
@@ -380,6 +387,7 @@ class FrontEnd:
         """The step's buffers as a ctr_step_t for ctr_step_run (built once)."""
         if getattr(self, "_native", None) is not None:
             return self._native
+        assert not getattr(self, "pad_r", False), "the native step runner needs contiguous R"
         w = self.w
         d = ctr.CtrStep()
         P = lambda t: None if t is None else t.data_ptr()
