@@ -326,8 +326,8 @@ __device__ __forceinline__ void load_row_block(const float* __restrict__ zb, int
   }
 }
 
-// FB: 32-row blocks covering F (F <= 32*FB); KS: dim / 16 (k-steps of 16).  Only two row
-// blocks of fragments are live at a time (the J block is re-read, from L1/L2).
+// FB: 32-row blocks covering F (F <= 32*FB); KS: dim / 16 (k-steps of 16).  All FB row
+// blocks of fragments stay in registers.
 template <int FB, int KS, bool SELF>
 __global__ __launch_bounds__(kThreads) void interaction_fwd_mfma_kernel(
     const float* __restrict__ Z, int64_t batch, int F, float* __restrict__ R, int64_t r_stride) {
@@ -340,27 +340,24 @@ __global__ __launch_bounds__(kThreads) void interaction_fwd_mfma_kernel(
   const int rl = lane & 31, kg = lane >> 5;
   for (int c = lane; c < dim; c += 64) rb[c] = zb[c];   // dense passthrough (exact)
 
+  // every row block of the sample in registers, all loads issued before any MFMA: each
+  // block is read once (re-reading block J for every tile (I, J) left Large's forward at
+  // 0.44 ms against 0.29)
+  bf16x8 fr[FB][KS];
+#pragma unroll
+  for (int I = 0; I < FB; ++I) load_row_block<KS>(zb, F, I, rl, kg, fr[I]);
 #pragma unroll
   for (int I = 0; I < FB; ++I) {
     if (32 * I >= F) break;
-    bf16x8 fa[KS];
-    load_row_block<KS>(zb, F, I, rl, kg, fa);
 #pragma unroll
     for (int J = 0; J <= I; ++J) {
       if (!SELF && J == I && F - 32 * I < 2) break;  // no pair i > j inside this tile
-      bf16x8 fb[KS];
-      if (J == I) {
-#pragma unroll
-        for (int s = 0; s < KS; ++s) fb[s] = fa[s];
-      } else {
-        load_row_block<KS>(zb + pinned_zero(), F, J, rl, kg, fb);
-      }
       f32x16 acc;
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[v] = 0.f;
 #pragma unroll
       for (int s = 0; s < KS; ++s)
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[s], fb[s], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[I][s], fr[J][s], acc, 0, 0, 0);
       // acc[v] = D[m][n], m = 8*(v/4) + 4*kg + v%4 (row, from A = block I), n = rl (from B)
       const int j = 32 * J + rl;
 #pragma unroll
