@@ -1,0 +1,90 @@
+// ctr_launch.h -- host declarations of the kernel launchers shared by the libctr sources
+// (the device helpers are in ctr_internal.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace ctr {
+
+// ----------------------------------------------------------------------------- launchers
+// Each returns hipSuccess or the launch error.  Shapes are validated by the caller.
+
+// unique.hip
+size_t unique_workspace_bytes(int64_t n);
+hipError_t launch_unique(const void* ids, bool ids64, int64_t n, const int64_t* offsets,
+                         int64_t batch, int32_t num_tables, const int64_t* row_base,
+                         int64_t modulus, int key_bits, bool key_signed, int64_t* uniq,
+                         int32_t* inverse, int32_t* num_unique, int32_t* perm,
+                         int32_t* seg_offsets, int4* sorted_src, void* workspace,
+                         hipStream_t s);
+
+// embbag.hip
+hipError_t launch_embbag_fwd(const void* table, bool bf16, int64_t total_rows, int dim,
+                             const int64_t* row_base, int32_t num_tables, const void* idx,
+                             bool idx64, int64_t nnz, const int64_t* offsets, int64_t batch,
+                             float* out, int64_t sb, int64_t st, hipStream_t s);
+hipError_t launch_gather_rows(const void* table, bool bf16, int64_t total_rows, int dim,
+                              const int64_t* rows, const int32_t* num_rows, int64_t capacity,
+                              float* out, hipStream_t s);
+hipError_t launch_sparse_sgd(void* table, bool bf16, int64_t total_rows, int dim,
+                             const int64_t* uniq, const int32_t* num_unique, int64_t capacity,
+                             const float* g, float lr, bool stochastic, uint64_t seed,
+                             hipStream_t s);
+hipError_t launch_init_table(void* table, bool bf16, int dim, int64_t row_begin,
+                             int64_t rows, float scale, uint64_t seed, hipStream_t s);
+hipError_t launch_validate_csr(const void* idx, bool idx64, int64_t nnz, const int64_t* offsets,
+                               int64_t batch, int32_t num_tables, const int64_t* row_base,
+                               int64_t total_rows, int32_t* bad, hipStream_t s);
+
+// segreduce.hip
+size_t embbag_bwd_workspace_bytes(int64_t nnz, int dim);
+hipError_t launch_embbag_bwd(const void* grad, bool grad_bf16, int64_t sb, int64_t st,
+                             const int64_t* offsets,
+                             int64_t batch, int32_t num_tables, int dim, int64_t nnz,
+                             const int32_t* perm, const int32_t* inverse, const int4* sorted_src,
+                             const int32_t* num_unique, float* row_grads, void* table,
+                             int sgd_mode, int64_t total_rows, const int64_t* uniq, float lr,
+                             uint64_t seed, void* workspace, hipStream_t s);
+
+// dict.hip
+hipError_t launch_dict_build(const int64_t* keys, const int32_t* rows, const int32_t* hot_slots,
+                             int64_t n, void* slots, int64_t capacity, int32_t* status,
+                             hipStream_t s);
+hipError_t launch_dict_lookup(const int64_t* ids, int64_t n, const void* slots,
+                              int64_t capacity, int64_t* values, hipStream_t s);
+hipError_t launch_dict_pool(const int64_t* values, int64_t nnz, const int64_t* offsets,
+                            int64_t batch, int32_t num_tables, const void* hot,
+                            int64_t hot_rows, const void* cold, int64_t cold_rows, bool bf16,
+                            int dim, float* out, int64_t sb, int64_t st, hipStream_t s);
+
+// interaction.hip
+bool interaction_bf16_supported(int F, int dim, bool self);
+bool interaction_f32_supported(int F, int dim, bool self);
+hipError_t launch_interaction_fwd(const float* Z, int64_t batch, int F, int dim, bool bf16,
+                                  bool self, float* R, int64_t r_stride, hipStream_t s);
+hipError_t launch_interaction_bwd(const float* Z, const float* dR, int64_t dr_stride,
+                                  int64_t batch, int F, int dim, bool bf16, bool self,
+                                  bool out_bf16, void* dZ, hipStream_t s);
+hipError_t launch_fm_fwd(const float* Z, int64_t batch, int F, int dim, float* out,
+                         hipStream_t s);
+hipError_t launch_fm_bwd(const float* Z, const float* dout, int64_t batch, int F, int dim,
+                         float* dZ, hipStream_t s);
+
+// dense.hip: fully connected layers and the logistic head
+int dense_wgrad_splits(int64_t M, int N, int cols, bool bf16, int64_t* k_split);
+int dense_dx_splits(int64_t M, int N, int K, int64_t* k_split);
+size_t dense_bwd_workspace_bytes(int64_t M, int N, int K, bool bias, bool relu, bool bf16);
+hipError_t launch_dense_fwd(const float* X, int64_t xs, int64_t M, int K, const float* W,
+                            const float* b, int N, bool relu, bool bf16, float* Y, int64_t ys,
+                            hipStream_t s);
+hipError_t launch_dense_bwd_sgd(const float* X, int64_t xs, int64_t M, int K, float* W,
+                                float* b, int N, bool relu, const float* Y, int64_t ys,
+                                const void* dY, bool dy_bf16, int64_t dys, bool bf16, float lr,
+                                float* dX, int64_t dxs, void* workspace, hipStream_t s);
+hipError_t launch_logistic_ne(const float* logits, int64_t ls, const float* labels, int64_t M,
+                              float* prob, float* dlogits, int64_t dls, float* stats,
+                              hipStream_t s);
+
+}  // namespace ctr
