@@ -189,8 +189,11 @@ def cpu_baseline_variants(fe, w, seconds: float):
 def time_variants(fe, w, K: int):
     """The interaction variants on the workload's Z (after the timed steps), each call alone
     bracketed by HIP events: the pair set with self-dots, forward and backward (P = F(F+1)/2),
-    and the FM sum by the squared-norm identity.  Algorithmic bytes: self forward
-    4BFd + 4B(d+P), backward 4B(d+P) + 8BFd; FM forward 4BFd + 4B, backward 8BFd + 4B."""
+    and the FM sum by the squared-norm identity; and the fused forward (pooling and the
+    interaction in one call) beside the two calls it replaces, timed the same way.
+    Algorithmic bytes: self forward 4BFd + 4B(d+P), backward 4B(d+P) + 8BFd; FM forward
+    4BFd + 4B, backward 8BFd + 4B; fused forward the pooling's bytes plus the dense rows read
+    (4Bd) and R written (4B(d+P)), the separate pair that plus Z's re-read (4BFd)."""
     import torch
     from sparse_embedding_lookup_amd import ctr
 
@@ -212,6 +215,15 @@ def time_variants(fe, w, K: int):
         "fm_bwd": (ctr.ctr_fm_interaction_bwd(fe.Z, dout, dZ, prepare=True),
                    8 * B * F * d + 4 * B),
     }
+    Pd = F * (F - 1) // 2                              # the strict pair set of the step
+    pool = stage_bytes(w, 0)["embbag_fwd"]
+    fused = pool + 4 * B * d + 4 * B * (d + Pd)
+    calls["embbag_interaction_fwd"] = (fe._c_embbag_interaction_fwd, fused)
+
+    def separate():
+        fe._c_embbag_fwd()
+        fe._c_interaction_fwd()
+    calls["embbag_fwd+interaction_fwd"] = (separate, fused + 4 * B * F * d)
     res = {}
     for name, (call, nbytes) in calls.items():
         for _ in range(3):
@@ -285,6 +297,8 @@ def time_dlrm(fe, w, K: int):
     flops = s.mlp_flops()
     big = max(layers, key=lambda kv: kv[1]["K"] * kv[1]["N"])
     return {
+        "forward": ("fused: ctr_embbag_interaction_fwd" if s.fe.fused_fwd else
+                    "separate: ctr_embbag_fwd, ctr_dot_interaction_fwd"),
         "mlp": {"bottom": [13, *workloads.DLRM_BOTTOM, w.dim],
                 "top": [w.dim + w.P, *workloads.DLRM_TOP, 1], "compute": kind},
         "step_ms": round(step_ms, 5),

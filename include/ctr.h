@@ -245,6 +245,29 @@ int32_t ctr_dot_interaction_fwd(const float* Z, int64_t batch, int32_t num_vecto
                                 int32_t compute, float* R, int64_t r_stride, void* stream);
 
 /*
+ * ctr_embbag_interaction_fwd -- the pooling of ctr_embbag_fwd ([DHEN] 2.1) and the dot
+ * interaction of ctr_dot_interaction_fwd ([DLRM] 02, [DHEN] 3.1 and Solution 2) in one pass.
+ * Z: fp32 [batch, F, dim], contiguous, F = num_tables + 1.  Row Z[b, 0, :] (the dense vector)
+ * is read; rows Z[b, 1 + t, :] are written with the pooled bags, exactly as ctr_embbag_fwd
+ * with out = Z + dim, out_stride_b = F*dim, out_stride_t = dim would write them (up to the
+ * order in which a bag's rows are added).  R receives what ctr_dot_interaction_fwd(Z, ...,
+ * compute, R, r_stride) computes from that Z, taken from an on-chip copy of the pooled
+ * vectors instead of a second read of Z; with compute = CTR_BF16 the copy is the bf16
+ * (nearest-even) rounding of the fp32 pooled vectors, as the separate call rounds them.
+ * table, dtype, total_rows, dim, row_base, num_tables, indices, index_type, nnz, offsets,
+ * batch: as ctr_embbag_fwd.  Supported: dim / (values per 16 bytes) a power of two up to 32,
+ * num_tables <= 256, one sample's pooled copy within 46 KiB (bf16 compute: F*(dim+8)*2 bytes,
+ * fp32: F*(dim+1)*4); compute = CTR_BF16 needs dim in {16, 32, 64, 128} and F <= 128.  Other
+ * shapes return CTR_ERR_UNSUPPORTED (the two separate calls cover them).  Z and R must not
+ * overlap the table, indices or offsets.
+ */
+int32_t ctr_embbag_interaction_fwd(const void* table, int32_t dtype, int64_t total_rows,
+                                   int32_t dim, const int64_t* row_base, int32_t num_tables,
+                                   const void* indices, int32_t index_type, int64_t nnz,
+                                   const int64_t* offsets, int64_t batch, float* Z,
+                                   int32_t compute, float* R, int64_t r_stride, void* stream);
+
+/*
  * ctr_dot_interaction_bwd -- chain rule of the above.  With dP_ij = dR[b*dr_stride + dim +
  * i*(i-1)/2 + j] for i > j:
  *   dZ[b, i, :] = sum over j != i of dP_(max(i,j), min(i,j)) * Z[b, j, :]

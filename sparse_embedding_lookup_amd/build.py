@@ -15,7 +15,7 @@ LIB = os.path.join(HERE, "libctr.so")
 OBJ = os.path.join(HERE, "_build")
 
 SOURCES = ["capi.cpp", "step.cpp", "unique.hip", "embbag.hip", "segreduce.hip", "interaction.hip",
-           "dict.hip", "dense.hip"]
+           "dict.hip", "dense.hip", "fused.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

@@ -439,6 +439,42 @@ int32_t ctr_dot_interaction_fwd(const float* Z, int64_t batch, int32_t num_vecto
                                 "ctr_dot_interaction_fwd");
 }
 
+int32_t ctr_embbag_interaction_fwd(const void* table, int32_t dtype, int64_t total_rows,
+                                   int32_t dim, const int64_t* row_base, int32_t num_tables,
+                                   const void* indices, int32_t index_type, int64_t nnz,
+                                   const int64_t* offsets, int64_t batch, float* Z,
+                                   int32_t compute, float* R, int64_t r_stride, void* stream) {
+  g_msg[0] = 0;
+  int32_t st = check_table(table, dtype, total_rows, dim);
+  if (st) return st;
+  if (index_type != CTR_I32 && index_type != CTR_I64)
+    return fail(CTR_ERR_INVALID_ARGUMENT, "index_type %d is not CTR_I32 or CTR_I64", index_type);
+  if (num_tables < 1) return fail(CTR_ERR_INVALID_ARGUMENT, "num_tables must be >= 1");
+  if (batch < 0 || (int64_t)num_tables * batch > kMaxElems ||
+      batch * (num_tables + 1) * (int64_t)dim > ((int64_t)1 << 40))
+    return fail(CTR_ERR_INVALID_ARGUMENT, "bad batch %lld", (long long)batch);
+  if (nnz < 0 || nnz > kMaxElems) return fail(CTR_ERR_INVALID_ARGUMENT, "bad nnz");
+  if (compute != CTR_F32 && compute != CTR_BF16)
+    return fail(CTR_ERR_INVALID_ARGUMENT, "compute %d is not CTR_F32 or CTR_BF16", compute);
+  if (batch > 0 && (!offsets || !Z || !R))
+    return fail(CTR_ERR_INVALID_ARGUMENT, "offsets, Z and R are required");
+  if (nnz > 0 && !indices) return fail(CTR_ERR_INVALID_ARGUMENT, "indices is NULL");
+  const int64_t F = (int64_t)num_tables + 1;
+  if (r_stride < dim + F * (F - 1) / 2)
+    return fail(CTR_ERR_INVALID_ARGUMENT, "r_stride %lld < dim + P", (long long)r_stride);
+  if (Z && !aligned16(Z)) return fail(CTR_ERR_UNSUPPORTED, "Z is not 16-byte aligned");
+  if (!ctr::embbag_interaction_supported(num_tables, dim, dtype == CTR_BF16, compute == CTR_BF16))
+    return fail(CTR_ERR_UNSUPPORTED,
+                "fused shape: dim/(values per 16 bytes) a power of two <= 32, num_tables <= 256, "
+                "one sample's pooled copy <= 46 KiB; bf16 compute: dim in {16,32,64,128}, F <= 128");
+  return hip_status(ctr::launch_embbag_interaction_fwd(table, dtype == CTR_BF16, total_rows, dim,
+                                                       row_base, num_tables, indices,
+                                                       index_type == CTR_I64, nnz, offsets, batch,
+                                                       Z, compute == CTR_BF16, R, r_stride,
+                                                       (hipStream_t)stream),
+                    "ctr_embbag_interaction_fwd");
+}
+
 int32_t ctr_dot_interaction_bwd(const float* Z, const float* dR, int64_t dr_stride,
                                 int64_t batch, int32_t num_vectors, int32_t dim, int32_t compute,
                                 float* dZ, void* stream) {

@@ -72,6 +72,14 @@ hipError_t launch_fm_fwd(const float* Z, int64_t batch, int F, int dim, float* o
 hipError_t launch_fm_bwd(const float* Z, const float* dout, int64_t batch, int F, int dim,
                          float* dZ, hipStream_t s);
 
+// fused.hip: pooling and the dot interaction in one pass
+bool embbag_interaction_supported(int num_tables, int dim, bool table_bf16, bool bf16);
+hipError_t launch_embbag_interaction_fwd(const void* table, bool table_bf16, int64_t total_rows,
+                                         int dim, const int64_t* row_base, int num_tables,
+                                         const void* idx, bool idx64, int64_t nnz,
+                                         const int64_t* offsets, int64_t batch, float* Z,
+                                         bool bf16, float* R, int64_t r_stride, hipStream_t s);
+
 // dense.hip: fully connected layers and the logistic head
 int dense_wgrad_splits(int64_t M, int N, int cols, bool bf16, int64_t* k_split);
 int dense_dx_splits(int64_t M, int N, int K, int64_t* k_split);

@@ -28,7 +28,7 @@ EXPORTED = [
     "ctr_dot_interaction_self_fwd", "ctr_dot_interaction_self_bwd", "ctr_fm_interaction_fwd",
     "ctr_fm_interaction_bwd", "ctr_dict_build", "ctr_dict_lookup", "ctr_dict_embbag_fwd",
     "ctr_dot_interaction_bwd_ex", "ctr_embbag_bwd_sgd_ex", "ctr_step_run_deep",
-    "ctr_dense_fwd", "ctr_dense_bwd_sgd", "ctr_logistic_ne",
+    "ctr_dense_fwd", "ctr_dense_bwd_sgd", "ctr_logistic_ne", "ctr_embbag_interaction_fwd",
 ]
 
 CTR_STEP_POOLED_INTERACTION, CTR_STEP_BATCH_MATRIX = 0, 1
@@ -106,6 +106,8 @@ def load() -> ctypes.CDLL:
         "ctr_dict_embbag_fwd": (i32, [P, i64, P, i64, i32, P, i64, P, i64, i32, i32, P, i64,
                                       i64, P]),
         "ctr_dot_interaction_fwd": (i32, [P, i64, i32, i32, i32, P, i64, P]),
+        "ctr_embbag_interaction_fwd": (i32, [P, i32, i64, i32, P, i32, P, i32, i64, P, i64, P,
+                                             i32, P, i64, P]),
         "ctr_dot_interaction_bwd": (i32, [P, P, i64, i64, i32, i32, i32, P, P]),
         "ctr_init_table_hash": (i32, [P, i32, i32, P, i32, u64, P]),
         "ctr_validate_csr": (i32, [P, i32, i64, P, i64, i32, P, i64, P, P]),
@@ -383,6 +385,25 @@ def ctr_dot_interaction_fwd(Z: torch.Tensor, compute: int = CTR_F32,
         R = torch.empty((B, d + P), dtype=torch.float32, device=Z.device)
     args = (_ptr(Z), B, F, d, compute, _ptr(R), R.stride(0))
     return _run("ctr_dot_interaction_fwd", args, stream, prepare, R)
+
+
+def ctr_embbag_interaction_fwd(table: torch.Tensor, indices: torch.Tensor,
+                               offsets: torch.Tensor, Z: torch.Tensor, compute: int = CTR_F32,
+                               R: Optional[torch.Tensor] = None,
+                               row_base: Optional[torch.Tensor] = None, stream=None,
+                               prepare: bool = False):
+    """Pooling into Z[:, 1:, :] and the dot interaction of Z into R in one call; Z[:, 0, :]
+    (the dense vectors) is an input."""
+    total_rows, dim = table.shape
+    B, F, d = Z.shape
+    assert d == dim and Z.is_contiguous()
+    P = F * (F - 1) // 2
+    if R is None:
+        R = torch.empty((B, d + P), dtype=torch.float32, device=Z.device)
+    args = (_ptr(table), _dtype_code(table), total_rows, dim, _ptr(row_base), F - 1,
+            _ptr(indices), _index_code(indices), indices.numel(), _ptr(offsets), B, _ptr(Z),
+            compute, _ptr(R), R.stride(0))
+    return _run("ctr_embbag_interaction_fwd", args, stream, prepare, R)
 
 
 def ctr_dot_interaction_bwd(Z: torch.Tensor, dR: torch.Tensor, compute: int = CTR_F32,

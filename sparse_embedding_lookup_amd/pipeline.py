@@ -36,7 +36,8 @@ class FrontEnd:
 
     def __init__(self, w: Workload, device="cuda", table: Optional[torch.Tensor] = None,
                  fused: bool = True, keep_grads: bool = False, pipelined: bool = False,
-                 rounding: str = "nearest", sr_seed: int = SR_SEED, pad_r: bool = False):
+                 rounding: str = "nearest", sr_seed: int = SR_SEED, pad_r: bool = False,
+                 fused_fwd: bool = False):
         """fused: the backward applies the sparse SGD as each row gradient completes
         (ctr_embbag_bwd_sgd); otherwise ctr_embbag_bwd then ctr_sparse_sgd.  keep_grads: also
         keep the per-row gradients in self.row_grads (always kept when not fused).
@@ -47,7 +48,10 @@ class FrontEnd:
         seed ctr_sr_step_seed(sr_seed, k).
         pad_r: R's rows start on 16-byte boundaries (stride rounded up to 4 floats), so that a
         layer reading R loads it with vector loads; R is then a strided view (the native step
-        runner, which assumes contiguous R, refuses it)."""
+        runner, which assumes contiguous R, refuses it).
+        fused_fwd: the forward is one call, ctr_embbag_interaction_fwd (pooling into Z and the
+        interaction from an on-chip copy of the pooled vectors), instead of ctr_embbag_fwd
+        then ctr_dot_interaction_fwd (pooled-interaction workloads only)."""
         assert rounding in ("nearest", "stochastic")
         assert rounding == "nearest" or w.dtype == "bf16", "stochastic rounding: bf16 tables"
         self.rounding = rounding
@@ -56,6 +60,7 @@ class FrontEnd:
         self.w = w
         self.pipelined = pipelined
         self.fused = fused
+        self.fused_fwd = bool(fused_fwd and w.interaction)
         self.keep_grads = keep_grads or not fused
         self.device = torch.device(device)
         self.bf16 = w.dtype == "bf16"
@@ -142,6 +147,9 @@ class FrontEnd:
                 self.table, self.indices, self.offsets, w.batch, w.num_tables, self.Z[:, 1:, :],
                 F * d, d, row_base=self.row_base, **P)
             self._c_interaction_fwd = ctr.ctr_dot_interaction_fwd(self.Z, self.compute, self.R, **P)
+            self._c_embbag_interaction_fwd = ctr.ctr_embbag_interaction_fwd(
+                self.table, self.indices, self.offsets, self.Z, self.compute, self.R,
+                row_base=self.row_base, **P)
             self._c_interaction_bwd = ctr.ctr_dot_interaction_bwd(self.Z, self.dR, self.compute,
                                                                   self.dZ, **P)
             if not self.fused:
@@ -188,6 +196,9 @@ class FrontEnd:
     def _interaction_fwd(self):
         self._c_interaction_fwd()
 
+    def _embbag_interaction_fwd(self):
+        self._c_embbag_interaction_fwd()
+
     def _interaction_bwd(self):
         self._c_interaction_bwd()
 
@@ -226,13 +237,18 @@ class FrontEnd:
         tail = ([("embbag_bwd_sgd", self._embbag_bwd_sgd)] if self.fused else
                 [("embbag_bwd", self._embbag_bwd), ("sparse_sgd", self._sparse_sgd)])
         if self.w.interaction:
-            return [("embbag_fwd", self._embbag_fwd), ("interaction_fwd", self._interaction_fwd),
-                    ("interaction_bwd", self._interaction_bwd), ("unique", self.unique)] + tail
+            fwd = ([("embbag_interaction_fwd", self._embbag_interaction_fwd)] if self.fused_fwd
+                   else [("embbag_fwd", self._embbag_fwd),
+                         ("interaction_fwd", self._interaction_fwd)])
+            return fwd + [("interaction_bwd", self._interaction_bwd),
+                          ("unique", self.unique)] + tail
         return [("unique", self.unique), ("gather_rows", self._gather_rows),
                 ("embbag_fwd", self._embbag_fwd)] + tail
 
     def forward(self):
-        if self.w.interaction:
+        if self.fused_fwd:
+            self._embbag_interaction_fwd()
+        elif self.w.interaction:
             self._embbag_fwd()
             self._interaction_fwd()
         else:
@@ -388,6 +404,7 @@ class FrontEnd:
         if getattr(self, "_native", None) is not None:
             return self._native
         assert not getattr(self, "pad_r", False), "the native step runner needs contiguous R"
+        assert not self.fused_fwd, "the native step runner makes the two forward calls"
         w = self.w
         d = ctr.CtrStep()
         P = lambda t: None if t is None else t.data_ptr()

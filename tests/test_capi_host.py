@@ -30,7 +30,8 @@ def _declared():
 def test_header_declares_expected_entry_points():
     names = _declared()
     for want in ["ctr_unique_ids", "ctr_gather_rows", "ctr_embbag_fwd", "ctr_embbag_bwd",
-                 "ctr_sparse_sgd", "ctr_dot_interaction_fwd", "ctr_dot_interaction_bwd"]:
+                 "ctr_sparse_sgd", "ctr_dot_interaction_fwd", "ctr_dot_interaction_bwd",
+                 "ctr_embbag_interaction_fwd"]:
         assert want in names
 
 
@@ -104,6 +105,45 @@ def test_embbag_fwd_bad_args():
     assert call(off=None) == ctr.CTR_ERR_INVALID_ARGUMENT
     assert call(T=0) == ctr.CTR_ERR_INVALID_ARGUMENT
     assert call(dim=2048) == ctr.CTR_ERR_UNSUPPORTED
+
+
+def test_embbag_interaction_fwd_bad_args():
+    lib = _lib()
+    # a valid call: 4 tables (F = 5) of d = 16 fp32, P = 10, so r_stride >= 26
+    ok = dict(table=FAKE, dtype=0, rows=100, dim=16, rb=None, T=4, idx=FAKE, it=1, nnz=10,
+              off=FAKE, B=10, Z=FAKE, c=0, R=FAKE, rs=26)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return lib.ctr_embbag_interaction_fwd(a["table"], a["dtype"], a["rows"], a["dim"],
+                                              a["rb"], a["T"], a["idx"], a["it"], a["nnz"],
+                                              a["off"], a["B"], a["Z"], a["c"], a["R"], a["rs"],
+                                              None)
+
+    assert call(table=None) == ctr.CTR_ERR_INVALID_ARGUMENT
+    assert call(dtype=5) == ctr.CTR_ERR_INVALID_ARGUMENT
+    assert call(dim=6) == ctr.CTR_ERR_UNSUPPORTED              # not a 16-byte multiple
+    assert call(it=3) == ctr.CTR_ERR_INVALID_ARGUMENT
+    assert call(T=0) == ctr.CTR_ERR_INVALID_ARGUMENT
+    assert call(nnz=-1) == ctr.CTR_ERR_INVALID_ARGUMENT
+    assert call(c=7) == ctr.CTR_ERR_INVALID_ARGUMENT
+    assert call(off=None) == ctr.CTR_ERR_INVALID_ARGUMENT
+    assert call(Z=None) == ctr.CTR_ERR_INVALID_ARGUMENT
+    assert call(R=None) == ctr.CTR_ERR_INVALID_ARGUMENT
+    assert call(idx=None) == ctr.CTR_ERR_INVALID_ARGUMENT
+    assert call(rs=25) == ctr.CTR_ERR_INVALID_ARGUMENT        # < dim + P
+    assert call(Z=MISALIGNED) == ctr.CTR_ERR_UNSUPPORTED
+    assert call(table=MISALIGNED) == ctr.CTR_ERR_UNSUPPORTED
+    assert call(dim=48, rs=58) == ctr.CTR_ERR_UNSUPPORTED             # 12 vectors: not a power of two
+    assert call(dim=256, rs=266) == ctr.CTR_ERR_UNSUPPORTED            # 64 vectors: above 32
+    assert call(T=300, rs=16 + 301 * 300 // 2) == ctr.CTR_ERR_UNSUPPORTED   # > 256 tables
+    assert call(c=1, dim=8, dtype=1) == ctr.CTR_ERR_UNSUPPORTED  # bf16 compute: dim >= 16
+    assert call(c=1, T=128, rs=16 + 129 * 128 // 2) == ctr.CTR_ERR_UNSUPPORTED   # F > 128
+    # an fp32 copy of one sample above 46 KiB: F = 101, d = 128 -> 52 KB
+    assert call(dim=128, T=100, rs=128 + 101 * 50) == ctr.CTR_ERR_UNSUPPORTED
+    assert b"fused shape" in lib.ctr_last_error()
+    # batch 0 is a no-op that launches nothing
+    assert call(B=0, nnz=0, idx=None, off=None, Z=None, R=None) == ctr.CTR_OK
 
 
 def test_embbag_bwd_workspace_and_bad_args():

@@ -53,6 +53,11 @@ def test_dlrm_step_stage_by_stage(name):
         assert_close(x, want, mag, RTOL_F32, "bottom layer %d" % i)
     Z = host(s.fe.Z)
     np.testing.assert_array_equal(Z[:, 0, :], x)
+    # pooled rows (the fused forward by default for matrix-core dots, else the two calls)
+    assert s.fe.fused_fwd == bf16
+    pooled, pmag = orc.embbag_fwd(orc.Table(w.rows, w.dim, w.dtype, w.table_seed), w.indices,
+                                  w.offsets, w.batch)
+    assert_close(Z[:, 1:, :], pooled, pmag, RTOL_F32, "pooled")
     R, Rm = orc.interaction_fwd(Z.astype(np.float64))
     Rg = host(s.fe.R)
     assert_close(Rg, R, Rm, rt_int, "R")
