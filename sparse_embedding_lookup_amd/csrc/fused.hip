@@ -19,7 +19,8 @@
 // through to R.
 // Phase 2 (interaction).  bf16: one wavefront per 32x32 lower-triangle tile of one sample on
 // v_mfma_f32_32x32x16_bf16, operands read from the LDS copy, fp32 accumulation, only i > j
-// written.  fp32: one thread per pair, fused multiply-adds in column order.
+// written.  fp32: four lanes per pair, each a chain of fused multiply-adds over every fourth
+// column, then summed across the four.
 #include "ctr_internal.h"
 
 namespace ctr {
@@ -34,6 +35,7 @@ constexpr int kBlockLds = 32768;            // block total aimed at: five blocks
 constexpr int kPoolLdsMax = 47104;          // with the static arrays (<= 16.1 KiB), under 64 KiB
 constexpr double kRowsPerGroup = 128.0;     // occurrences per lane group aimed at
 constexpr int64_t kMinBlocks = 2048;        // keep several blocks per CU where the batch allows
+constexpr double kMinRowsPerGroup = 20.0;   // ... unless a group's share would be shorter
 
 // Row i of the strict lower triangle that holds pair index q (i(i-1)/2 <= q < i(i+1)/2).
 __device__ __forceinline__ int pair_row(int q) {
@@ -296,15 +298,21 @@ void embbag_interaction_fwd_kernel(
       }
     }
   } else {
+    // four lanes per dot (columns k = part mod 4, fused multiply-adds in column order),
+    // joined by two shuffles; a quad of lanes is always active together
     const int P = F * (F - 1) / 2;
-    for (int e = tid; e < ns * P; e += kThreads) {
+    for (int e4 = tid; e4 < ns * P * 4; e4 += kThreads) {
+      const int e = e4 >> 2, part = e4 & 3;
       const int s = e / P, q = e - s * P;
       const int i = pair_row(q), j = q - i * (i - 1) / 2;
       const float* zi = poolf + (s * F + i) * kPitchF;
       const float* zj = poolf + (s * F + j) * kPitchF;
       float a = 0.f;
-      for (int k = 0; k < dim; ++k) a = fmaf(zi[k], zj[k], a);
-      R[(b0 + s) * r_stride + dim + q] = a;
+#pragma unroll 4
+      for (int k = part; k < dim; k += 4) a = fmaf(zi[k], zj[k], a);
+      a += __shfl_xor(a, 1, 64);
+      a += __shfl_xor(a, 2, 64);
+      if (part == 0) R[(b0 + s) * r_stride + dim + q] = a;
     }
   }
 }
@@ -337,6 +345,13 @@ FusedShape fused_shape(int T, int dim, bool tbf16, bool bf16, int64_t batch, int
   if (s_rows < S) S = s_rows;
   const int64_t s_blocks = batch / kMinBlocks;
   if (s_blocks < S) S = (int)(s_blocks > 1 ? s_blocks : 1);
+  // a share shorter than kMinRowsPerGroup leaves the load window half empty: take more
+  // samples per block (fewer blocks) then, within the LDS budget
+  const int s_lds = (int)(((size_t)kBlockLds - fixed) / per) > 1
+                        ? (int)(((size_t)kBlockLds - fixed) / per) : 1;
+  int s_min = (int)(kMinRowsPerGroup * kGroups / (rows > 1.0 ? rows : 1.0) + 0.999);
+  if (s_min > s_lds) s_min = s_lds;
+  if (S < s_min) S = s_min;
   if (S > kMaxBags / T) S = kMaxBags / T;
   if (S < 1) S = 1;
   f.ok = true;
