@@ -57,10 +57,12 @@ class DlrmStep:
         self.side = torch.cuda.Stream(device=self.device) if overlap else None
         # R padded to 16-byte rows: the top MLP's first layer reads it with vector loads
         # fused forward (pooling and interaction in one call) by default where the dots run
-        # on matrix cores: measured faster on the Criteo-shaped workload and even on Large;
-        # with fp32 dots (Small) the two separate calls are faster
+        # on matrix cores and a sample's vectors fit one 32-row tile (F <= 32): the Criteo-
+        # shaped step 1.278 -> 1.265 ms.  With 65 vectors (Large) a fused block gathers from
+        # every table at once while the batch's sort runs beside it: 15.08 -> 15.32 ms, so
+        # the two calls stay; with fp32 dots (Small) the two forms are level.
         if fused_fwd is None:
-            fused_fwd = w.compute == "bf16"
+            fused_fwd = w.compute == "bf16" and w.F <= 32
         self.fe = FrontEnd(w, device, table=table, pad_r=True, fused_fwd=fused_fwd)
         self.lr = float(w.lr if lr is None else lr)
         self.compute = self.fe.compute

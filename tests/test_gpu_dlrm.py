@@ -54,7 +54,7 @@ def test_dlrm_step_stage_by_stage(name):
     Z = host(s.fe.Z)
     np.testing.assert_array_equal(Z[:, 0, :], x)
     # pooled rows (the fused forward by default for matrix-core dots, else the two calls)
-    assert s.fe.fused_fwd == bf16
+    assert s.fe.fused_fwd == (bf16 and w.F <= 32)
     pooled, pmag = orc.embbag_fwd(orc.Table(w.rows, w.dim, w.dtype, w.table_seed), w.indices,
                                   w.offsets, w.batch)
     assert_close(Z[:, 1:, :], pooled, pmag, RTOL_F32, "pooled")
