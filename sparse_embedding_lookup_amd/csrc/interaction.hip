@@ -370,9 +370,11 @@ __global__ __launch_bounds__(kThreads) void interaction_fwd_mfma_kernel(
 }
 
 // ------------------------------------------------------------------------- bf16 backward
-// One wave per sample; WPB samples per block; LDS holds each sample's pair gradients.
-// For each 32-row block of S (A operand, built once from LDS) and each 32-column slab of Z
-// (B operand, re-read per row block from L1/L2), 2*FB MFMAs give a 32x32 block of dZ.
+// One wave per sample; WPB samples per block; LDS holds each sample's pair gradients, rounded
+// to bf16 once (they are matrix-core operands; doubling a self-dot's entry stays exact), which
+// halves the LDS a block needs.  For each 32-row block of S (A operand, built once from LDS)
+// and each 32-column slab of Z (B operand, re-read per row block from L1/L2), 2*FB MFMAs give
+// a 32x32 block of dZ.
 // OUTB: dZ is stored as bf16 (nearest-even of the fp32 accumulator) instead of fp32.
 template <int FB, int KS, bool SELF, bool OUTB>
 __global__ __launch_bounds__(kThreads) void interaction_bwd_mfma_kernel(
@@ -380,16 +382,17 @@ __global__ __launch_bounds__(kThreads) void interaction_bwd_mfma_kernel(
     int64_t batch, int F, int wpb, void* __restrict__ dZ) {
   constexpr int FKS = 2 * FB;             // k-steps of 16 over the padded F
   constexpr int dim = KS * 16;
-  extern __shared__ float sp_all[];
+  extern __shared__ __align__(16) unsigned char sp_raw[];
   const int lane = threadIdx.x & 63;
   const int wv = threadIdx.x >> 6;
   const int P = num_pairs<SELF>(F);
   const int64_t b = (int64_t)blockIdx.x * wpb + wv;
   const bool live = wv < wpb && b < batch;
-  float* sp = sp_all + wv * (P + 1);       // slot P holds 0: the padding (and the diagonal)
+  // slot P holds 0: the padding (and the diagonal); P + 2 slots keep 4-byte alignment
+  __bf16* sp = reinterpret_cast<__bf16*>(sp_raw) + wv * (P + 2);
   if (live) {
-    for (int q = lane; q < P; q += 64) sp[q] = dR[b * dr_stride + dim + q];
-    if (lane == 0) sp[P] = 0.f;
+    for (int q = lane; q < P; q += 64) sp[q] = (__bf16)dR[b * dr_stride + dim + q];
+    if (lane == 0) sp[P] = (__bf16)0.f;
   }
   __syncthreads();
   if (!live) return;
@@ -412,7 +415,6 @@ __global__ __launch_bounds__(kThreads) void interaction_bwd_mfma_kernel(
     bf16x8 af[FKS];
 #pragma unroll
     for (int s = 0; s < FKS; ++s) {
-      float x[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int j = 16 * s + 8 * kgx + e;
@@ -421,9 +423,8 @@ __global__ __launch_bounds__(kThreads) void interaction_bwd_mfma_kernel(
         const int ok = vi & vj & (SELF ? 1 : ne);
         const int q = ok * (SELF ? sym_pair_index<true>(i, j) : tri_index(i, j)) + (1 - ok) * P;
         // d<z_i, z_i>/dz_i = 2 z_i: the diagonal of S carries twice the self-dot gradient
-        x[e] = SELF ? sp[q] * (float)(2 - ne) : sp[q];
+        af[s][e] = SELF ? (__bf16)((float)sp[q] * (float)(2 - ne)) : sp[q];
       }
-      af[s] = pack_bf16x8(x);
     }
 #pragma unroll 1
     for (int nb = 0; nb < nblk; ++nb) {
@@ -634,10 +635,10 @@ hipError_t interaction_bwd(const float* Z, const float* dR, int64_t dr_stride, i
     return hipGetLastError();
   }
   const int FB = (F + 31) / 32;
-  int wpb = 65536 / ((P + 1) * 4);
+  int wpb = 65536 / ((P + 2) * 2);
   if (wpb > 4) wpb = 4;
   if (wpb < 1) wpb = 1;
-  const size_t lds = (size_t)wpb * (P + 1) * sizeof(float);
+  const size_t lds = (size_t)wpb * (P + 2) * sizeof(__bf16);
   const int64_t blocks = (batch + wpb - 1) / wpb;
   const int KS = dim / 16;
 #define CTR_BWD_MFMA(KS_)                                                                      \
