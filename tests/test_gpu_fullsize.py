@@ -144,6 +144,13 @@ def large_run():
     w = workloads.large()
     say("Large nnz", w.nnz)
     fe = FrontEnd(w, DEV, keep_grads=True)
+    # the fused forward at full size, into buffers of its own, before the step's update
+    fe.fused_Z = fe.Z.clone()                  # row 0 of each sample: the dense vector
+    fe.fused_R = torch.empty_like(fe.R)
+    ctr.ctr_embbag_interaction_fwd(fe.table, fe.indices, fe.offsets, fe.fused_Z, fe.compute,
+                                   fe.fused_R, row_base=fe.row_base)
+    torch.cuda.synchronize()
+    say("Large fused forward done")
     fe.step()
     torch.cuda.synchronize()
     say("Large step done")
@@ -197,6 +204,33 @@ def test_large_interaction_sampled(large_run):
         assert_close(R[b][None], Rw, Rm, 3 * RTOL_BF16, "Large R sample %d" % b)
         dZw, dZm = orc.interaction_bwd(Z, w.grad_out[b][None].astype(np.float64), Zm)
         assert_close(dZ[b][None], dZw, dZm, 3 * RTOL_BF16, "Large dZ sample %d" % b)
+
+
+@pytest.mark.timeout(900)
+def test_large_fused_forward_sampled(large_run):
+    """The fused pooling + interaction call at Large's full size: sampled samples' pooled
+    rows and R rows against the oracle, which pools every table of those samples itself."""
+    w, fe = large_run
+    rng = np.random.default_rng(3)
+    samples = rng.choice(w.batch, size=24, replace=False)
+    one = orc.Table(w.rows, w.dim, w.dtype, w.table_seed)
+    Zf = host(fe.fused_Z)
+    Rf = host(fe.fused_R)
+    for b in samples:
+        ids, lens = [], []
+        for t in range(w.num_tables):
+            s = t * w.batch + int(b)
+            ids.append(w.indices[w.offsets[s]:w.offsets[s + 1]])
+            lens.append(int(w.offsets[s + 1] - w.offsets[s]))
+        off = np.zeros(w.num_tables + 1, dtype=np.int64)
+        off[1:] = np.cumsum(lens)
+        pooled, pmag = orc.embbag_fwd(one, np.concatenate(ids), off, 1)
+        assert_close(Zf[b, 1:][None], pooled, pmag, RTOL_F32, "Large fused Z sample %d" % b)
+        np.testing.assert_array_equal(Rf[b, :w.dim], w.dense[b])
+        Z = np.concatenate([w.dense[b][None, None, :].astype(np.float64), pooled], axis=1)
+        Zm = np.concatenate([np.abs(w.dense[b])[None, None, :].astype(np.float64), pmag], axis=1)
+        Rw, Rm = orc.interaction_fwd(Z, Zm)
+        assert_close(Rf[b][None], Rw, Rm, 3 * RTOL_BF16, "Large fused R sample %d" % b)
 
 
 @pytest.mark.timeout(900)
