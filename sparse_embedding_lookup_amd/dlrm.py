@@ -49,11 +49,17 @@ class DlrmStep:
 
     def __init__(self, w: Workload, inputs: DlrmInputs, device="cuda",
                  table: Optional[torch.Tensor] = None, lr: Optional[float] = None,
-                 overlap: bool = True, fused_fwd: Optional[bool] = None):
+                 overlap: bool = True, fused_fwd: Optional[bool] = None,
+                 unique_at: str = "start"):
         assert w.interaction, "the DLRM step needs the pooled-interaction workload"
         self.w = w
         self.device = torch.device(device)
         self.overlap = overlap
+        # with overlap, where the batch's unique forks to the side stream: "start" (before
+        # the bottom MLP) or "after_pool" (after the pooling, so the sort overlaps the
+        # interaction and the MLPs instead of the HBM-bound gathers)
+        assert unique_at in ("start", "after_pool")
+        self.unique_at = unique_at
         self.side = torch.cuda.Stream(device=self.device) if overlap else None
         # R padded to 16-byte rows: the top MLP's first layer reads it with vector loads
         # fused forward (pooling and interaction in one call) by default where the dots run
@@ -111,12 +117,21 @@ class DlrmStep:
                             for L, x, y, dy, dx in zip(self.bottom, bx, self.b_out, b_dy,
                                                        self.b_dx)]
 
-    def forward(self):
+    def forward(self, after_pool=None):
         """Bottom MLP, pooling, interaction, top MLP and head (the head also leaves the
-        logits' gradient)."""
+        logits' gradient).  `after_pool` runs right after the pooling call."""
         for call in self._fwd_bottom:
             call()
-        self.fe.forward()                 # pooling and interaction (one call when fused_fwd)
+        fe = self.fe
+        if fe.fused_fwd:
+            fe._embbag_interaction_fwd()
+            if after_pool:
+                after_pool()
+        else:
+            fe._embbag_fwd()
+            if after_pool:
+                after_pool()
+            fe._interaction_fwd()
         for call in self._fwd_top:
             call()
         self._head()
@@ -147,16 +162,25 @@ class DlrmStep:
     def step(self):
         """One training step: forward, head, backward with every SGD update."""
         fe = self.fe
-        if self.overlap:
+        if not self.overlap:
+            fe.unique()
+            self.forward()
+            self.backward()
+            return
+
+        def fork_unique():
             # the unique of this batch on the side stream, after everything enqueued so far
             # (so after the previous step's backward, which read the unique outputs)
             main = torch.cuda.current_stream(self.device)
             self.side.wait_stream(main)
             with torch.cuda.stream(self.side):
                 fe.unique()
+
+        if self.unique_at == "start":
+            fork_unique()
+            self.forward()
         else:
-            fe.unique()
-        self.forward()
+            self.forward(after_pool=fork_unique)
         self.backward()
 
     def mlp_only(self):

@@ -152,13 +152,15 @@ def test_dlrm_training_lowers_the_loss():
 
 
 @pytest.mark.parametrize("graph", [False, True])
-def test_dlrm_overlapped_unique_matches_serial(graph):
-    """The unique on a side stream (overlap=True) gives the same bits as running it in line,
-    step after step, eager or replayed from a graph."""
+@pytest.mark.parametrize("unique_at", ["start", "after_pool"])
+def test_dlrm_overlapped_unique_matches_serial(graph, unique_at):
+    """The unique on a side stream (overlap=True), forked when the step starts or after the
+    pooling, gives the same bits as running it in line, step after step, eager or replayed
+    from a graph."""
     w = workloads.criteo(batch=128)
     inp = workloads.dlrm_inputs(w, seed=4)
     a = DlrmStep(w, inp, DEV, overlap=False)
-    b = DlrmStep(w, inp, DEV, overlap=True)
+    b = DlrmStep(w, inp, DEV, overlap=True, unique_at=unique_at)
     g = b.capture(steps=1) if graph else None
     for k in range(3):
         a.step()
