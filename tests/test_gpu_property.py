@@ -3,8 +3,8 @@ draws the same examples): each call of the path against the oracle, and a whole 
 step on random little workloads.
 
 Shapes are drawn across the kernels' boundaries: n from 0, keys over 1 to 62 bits and of
-either sign, 1 to 4 tables with empty bags, every supported row width, F from 2 up to past
-one 32-row MFMA block, batches that leave ragged blocks.  The bars are the parity bars: the
+either sign, 1 to 4 tables with empty bags (up to 40 for the fused forward), every supported
+row width, F from 2 up to past one 32-row MFMA block, batches that leave ragged blocks.  The bars are the parity bars: the
 ID work bit-exact, floating point within rtol times the oracle's sum of |terms|.
 """
 import numpy as np
@@ -146,3 +146,44 @@ def test_whole_step_property(c, dtype, wide):
     untouched = np.ones(sum(rows), bool)
     untouched[o["uniq"]] = False
     np.testing.assert_array_equal(tbl[untouched], before[untouched])
+
+
+@SETTINGS
+@given(T=st.integers(1, 40), B=st.integers(1, 300), tdt=st.sampled_from(["f32", "bf16"]),
+       compute=st.sampled_from(["f32", "bf16"]), wide=st.integers(0, 3),
+       empty=st.sampled_from([0.0, 0.3]), max_len=st.integers(1, 12),
+       seed=st.integers(0, 2 ** 31 - 1))
+def test_fused_forward_property(T, B, tdt, compute, wide, empty, max_len, seed):
+    """ctr_embbag_interaction_fwd on random shapes: Z's pooled rows against the oracle's
+    pooling, R against the oracle's interaction of the kernel's own Z."""
+    dim = [16, 32, 64, 128][wide]
+    F = T + 1
+    if compute == "bf16" and F > 128:
+        return
+    per = F * (dim + 8) * 2 if compute == "bf16" else F * (dim + 1) * 4
+    if per > 47104:                       # one sample's copy beyond what one block holds
+        return
+    say("fused forward property", T, B, tdt, compute, dim, empty, max_len)
+    rng = np.random.default_rng(seed)
+    rows = [int(r) for r in rng.integers(1, 400, size=T)]
+    lengths = rng.integers(1, max_len + 1, size=(T, B))
+    lengths[rng.random((T, B)) < empty] = 0
+    off = np.zeros(T * B + 1, dtype=np.int64)
+    off[1:] = np.cumsum(lengths.reshape(-1))
+    ids = np.concatenate([rng.integers(0, rows[t], int(lengths[t].sum())) for t in range(T)])
+    ids = ids.astype(np.int64)
+    t = gpu_table(rows, dim, tdt, seed % 1000)
+    tab = orc.Table(rows, dim, tdt, seed % 1000)
+    dense = rng.standard_normal((B, dim)).astype(np.float32)
+    Z = torch.full((B, F, dim), float("nan"), device=DEV)
+    Z[:, 0, :] = dev(dense)
+    code = ctr.CTR_BF16 if compute == "bf16" else ctr.CTR_F32
+    R = ctr.ctr_embbag_interaction_fwd(t, dev(ids), dev(off), Z, code,
+                                       row_base=dev(tab.row_base))
+    Zg, Rg = host(Z), host(R)
+    want, mag = orc.embbag_fwd(tab, ids, off, B)
+    assert_close(Zg[:, 1:], want, mag, RTOL_F32, "fused Z property")
+    np.testing.assert_array_equal(Rg[:, :dim], dense)
+    want, mag = orc.interaction_fwd(Zg.astype(np.float64))
+    assert_close(Rg, want, mag, RTOL_BF16 if compute == "bf16" else RTOL_F32,
+                 "fused R property")
