@@ -240,12 +240,20 @@ void orc_embbag_fwd(const float* data, uint64_t seed, const int64_t* row_base,
 }
 
 /* ------------------------------------------------------------------ a6: interaction */
+/* A factor of a pair product: the value itself, or (bf16 != 0) the value rounded to bf16
+ * nearest-even.  The bf16 form is the reading taken for workloads whose tables are stored in
+ * bf16 with fp32 accumulation: the interaction's operands (Z, and the pair gradients in the
+ * backward) are rounded to bf16 once, their products and sums are exact here. */
+static double operand(double x, int32_t bf16) { return bf16 ? orc_round_bf16(x) : x; }
+
 /* [DLRM] 02 and [DHEN] 3.1 / Solution 2: for each sample, the dense vector z_0 followed by
  * the dot products <z_i, z_j> of every pair i > j (strict: C(F,2) of them), in the order
- * of the row-major strict lower triangle, index i(i-1)/2 + j.
- * Z, zmag: [batch][F][dim] (zmag may be NULL: |Z|); R, rmag: [batch][dim + P]. */
+ * of the row-major strict lower triangle, index i(i-1)/2 + j.  The dense part of R is z_0
+ * as it is (a copy, never rounded).
+ * Z, zmag: [batch][F][dim] (zmag may be NULL: the absolute values of the factors);
+ * R, rmag: [batch][dim + P]; bf16: factors rounded to bf16 (operand() above). */
 void orc_interaction_fwd(const double* Z, const double* zmag, int64_t batch, int32_t F,
-                         int32_t dim, double* R, double* rmag) {
+                         int32_t dim, int32_t bf16, double* R, double* rmag) {
   int64_t P = (int64_t)F * (F - 1) / 2, W = dim + P;
 #pragma omp parallel for schedule(static)
   for (int64_t b = 0; b < batch; ++b) {
@@ -259,9 +267,10 @@ void orc_interaction_fwd(const double* Z, const double* zmag, int64_t batch, int
       for (int64_t j = 0; j < i; ++j) {
         double s = 0.0, a = 0.0;
         for (int64_t c = 0; c < dim; ++c) {
-          s += z[i * dim + c] * z[j * dim + c];
-          double mi = zm ? zm[i * dim + c] : fabs(z[i * dim + c]);
-          double mj = zm ? zm[j * dim + c] : fabs(z[j * dim + c]);
+          double xi = operand(z[i * dim + c], bf16), xj = operand(z[j * dim + c], bf16);
+          s += xi * xj;
+          double mi = zm ? zm[i * dim + c] : fabs(xi);
+          double mj = zm ? zm[j * dim + c] : fabs(xj);
           a += mi * mj;
         }
         R[b * W + dim + i * (i - 1) / 2 + j] = s;
@@ -273,9 +282,12 @@ void orc_interaction_fwd(const double* Z, const double* zmag, int64_t batch, int
 /* ------------------------------------------------------------------ a7: its gradient */
 /* Chain rule of the interaction above: with dP_ij the upstream gradient of pair (i, j),
  * dZ_i = sum over j != i of dP_(max(i,j), min(i,j)) * z_j, and the upstream gradient of
- * the dense passthrough adds to dZ_0.  dR: [batch][dim + P]; dZ, dmag: [batch][F][dim]. */
+ * the dense passthrough adds to dZ_0.  dR: [batch][dim + P]; dZ, dmag: [batch][F][dim].
+ * bf16: dP and z_j rounded to bf16 (operand()); the dense passthrough's gradient is added as
+ * it is. */
 void orc_interaction_bwd(const double* Z, const double* zmag, const double* dR,
-                         int64_t batch, int32_t F, int32_t dim, double* dZ, double* dmag) {
+                         int64_t batch, int32_t F, int32_t dim, int32_t bf16, double* dZ,
+                         double* dmag) {
   int64_t P = (int64_t)F * (F - 1) / 2, W = dim + P;
 #pragma omp parallel for schedule(static)
   for (int64_t b = 0; b < batch; ++b) {
@@ -288,9 +300,10 @@ void orc_interaction_bwd(const double* Z, const double* zmag, const double* dR,
         for (int64_t j = 0; j < F; ++j) {
           if (j == i) continue;
           int64_t hi = i > j ? i : j, lo = i > j ? j : i;
-          double gp = g[dim + hi * (hi - 1) / 2 + lo];
-          s += gp * z[j * dim + c];
-          a += fabs(gp) * (zm ? zm[j * dim + c] : fabs(z[j * dim + c]));
+          double gp = operand(g[dim + hi * (hi - 1) / 2 + lo], bf16);
+          double zj = operand(z[j * dim + c], bf16);
+          s += gp * zj;
+          a += fabs(gp) * (zm ? zm[j * dim + c] : fabs(zj));
         }
         if (i == 0) {
           s += g[c];
@@ -350,9 +363,9 @@ void orc_sparse_sgd(const float* data, uint64_t seed, const int64_t* row_base,
 /* ------------------------------------------------------------------ interaction variants */
 /* [DHEN] 3.1: all inner products <x_i, x_j> for i <= j, self-dots included.  Pairs i >= j of
  * z_0..z_{F-1} in row-major lower-triangle order, index i(i+1)/2 + j; R = [z_0 | pairs],
- * P = F(F+1)/2.  Magnitudes as in orc_interaction_fwd. */
+ * P = F(F+1)/2.  Magnitudes and the bf16 factors as in orc_interaction_fwd. */
 void orc_interaction_self_fwd(const double* Z, const double* zmag, int64_t batch, int32_t F,
-                              int32_t dim, double* R, double* rmag) {
+                              int32_t dim, int32_t bf16, double* R, double* rmag) {
   int64_t P = (int64_t)F * (F + 1) / 2, W = dim + P;
 #pragma omp parallel for schedule(static)
   for (int64_t b = 0; b < batch; ++b) {
@@ -366,9 +379,10 @@ void orc_interaction_self_fwd(const double* Z, const double* zmag, int64_t batch
       for (int64_t j = 0; j <= i; ++j) {
         double s = 0.0, a = 0.0;
         for (int64_t c = 0; c < dim; ++c) {
-          s += z[i * dim + c] * z[j * dim + c];
-          double mi = zm ? zm[i * dim + c] : fabs(z[i * dim + c]);
-          double mj = zm ? zm[j * dim + c] : fabs(z[j * dim + c]);
+          double xi = operand(z[i * dim + c], bf16), xj = operand(z[j * dim + c], bf16);
+          s += xi * xj;
+          double mi = zm ? zm[i * dim + c] : fabs(xi);
+          double mj = zm ? zm[j * dim + c] : fabs(xj);
           a += mi * mj;
         }
         R[b * W + dim + i * (i + 1) / 2 + j] = s;
@@ -379,9 +393,11 @@ void orc_interaction_self_fwd(const double* Z, const double* zmag, int64_t batch
 
 /* Chain rule of the pair set with self-dots: dZ_i = sum over j != i of dP_(max,min) z_j
  * + 2 dP_ii z_i (the derivative of <z_i, z_i>), plus the dense passthrough's gradient on
- * dZ_0.  dR: [batch][dim + F(F+1)/2]. */
+ * dZ_0.  dR: [batch][dim + F(F+1)/2]; bf16 as in orc_interaction_bwd (the doubled self
+ * term is 2 times the rounded dP_ii). */
 void orc_interaction_self_bwd(const double* Z, const double* zmag, const double* dR,
-                              int64_t batch, int32_t F, int32_t dim, double* dZ, double* dmag) {
+                              int64_t batch, int32_t F, int32_t dim, int32_t bf16, double* dZ,
+                              double* dmag) {
   int64_t P = (int64_t)F * (F + 1) / 2, W = dim + P;
 #pragma omp parallel for schedule(static)
   for (int64_t b = 0; b < batch; ++b) {
@@ -393,10 +409,11 @@ void orc_interaction_self_bwd(const double* Z, const double* zmag, const double*
         double s = 0.0, a = 0.0;
         for (int64_t j = 0; j < F; ++j) {
           int64_t hi = i > j ? i : j, lo = i > j ? j : i;
-          double gp = g[dim + hi * (hi + 1) / 2 + lo];
+          double gp = operand(g[dim + hi * (hi + 1) / 2 + lo], bf16);
+          double zj = operand(z[j * dim + c], bf16);
           double k = (j == i) ? 2.0 : 1.0;
-          s += k * gp * z[j * dim + c];
-          a += k * fabs(gp) * (zm ? zm[j * dim + c] : fabs(z[j * dim + c]));
+          s += k * gp * zj;
+          a += k * fabs(gp) * (zm ? zm[j * dim + c] : fabs(zj));
         }
         if (i == 0) {
           s += g[c];

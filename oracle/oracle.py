@@ -53,12 +53,12 @@ def _load():
         "orc_unique": (i64, [P, i64, P, P, P, P]),
         "orc_gather_rows": (None, [P, u64, P, i32, i32, i32, P, i64, P]),
         "orc_embbag_fwd": (None, [P, u64, P, i32, i32, i32, P, P, i64, P, P]),
-        "orc_interaction_fwd": (None, [P, P, i64, i32, i32, P, P]),
-        "orc_interaction_bwd": (None, [P, P, P, i64, i32, i32, P, P]),
+        "orc_interaction_fwd": (None, [P, P, i64, i32, i32, i32, P, P]),
+        "orc_interaction_bwd": (None, [P, P, P, i64, i32, i32, i32, P, P]),
         "orc_embbag_bwd": (None, [P, P, P, i64, i32, i32, P, i64, P, P]),
         "orc_sparse_sgd": (None, [P, u64, P, i32, i32, i32, P, i64, P, P, f32, P, P]),
-        "orc_interaction_self_fwd": (None, [P, P, i64, i32, i32, P, P]),
-        "orc_interaction_self_bwd": (None, [P, P, P, i64, i32, i32, P, P]),
+        "orc_interaction_self_fwd": (None, [P, P, i64, i32, i32, i32, P, P]),
+        "orc_interaction_self_bwd": (None, [P, P, P, i64, i32, i32, i32, P, P]),
         "orc_fm_fwd": (None, [P, P, i64, i32, i32, P, P]),
         "orc_fm_bwd": (None, [P, P, P, i64, i32, i32, P, P]),
         "orc_dense_fwd": (None, [P, P, i64, i32, P, P, i32, i32, i32, P, P]),
@@ -193,47 +193,53 @@ def embbag_fwd(tab: Table, ids, offsets, batch: int):
 
 
 # ------------------------------------------------------------------------ a6, a7
-def interaction_fwd(Z, zmag=None):
+def interaction_fwd(Z, zmag=None, bf16: bool = False):
+    """R = [z_0 | <z_i, z_j> for i > j] per sample, with magnitudes.  bf16: every factor of a
+    pair product is rounded to bf16 nearest-even first (the products and sums stay exact)."""
     Z = _c(Z, np.float64)
     B, F, d = Z.shape
     zm = None if zmag is None else _c(zmag, np.float64)
     P = F * (F - 1) // 2
     R = np.empty((B, d + P), dtype=np.float64)
     Rm = np.empty_like(R)
-    _load().orc_interaction_fwd(_p(Z), _p(zm), B, F, d, _p(R), _p(Rm))
+    _load().orc_interaction_fwd(_p(Z), _p(zm), B, F, d, int(bool(bf16)), _p(R), _p(Rm))
     return R, Rm
 
 
-def interaction_bwd(Z, dR, zmag=None):
+def interaction_bwd(Z, dR, zmag=None, bf16: bool = False):
+    """dZ of the strict pair set, with magnitudes.  bf16: the pair gradients and z_j rounded to
+    bf16 nearest-even in the products; the dense passthrough's gradient is added as it is."""
     Z = _c(Z, np.float64)
     B, F, d = Z.shape
     dR = _c(dR, np.float64)
     zm = None if zmag is None else _c(zmag, np.float64)
     dZ = np.empty((B, F, d), dtype=np.float64)
     dm = np.empty_like(dZ)
-    _load().orc_interaction_bwd(_p(Z), _p(zm), _p(dR), B, F, d, _p(dZ), _p(dm))
+    _load().orc_interaction_bwd(_p(Z), _p(zm), _p(dR), B, F, d, int(bool(bf16)), _p(dZ),
+                                _p(dm))
     return dZ, dm
 
 
-def interaction_self_fwd(Z, zmag=None):
+def interaction_self_fwd(Z, zmag=None, bf16: bool = False):
     """Pairs i >= j (self-dots included), P = F(F+1)/2: R = [dense | pairs], with magnitudes."""
     Z = _c(Z, np.float64)
     B, F, d = Z.shape
     zm = None if zmag is None else _c(zmag, np.float64)
     R = np.empty((B, d + F * (F + 1) // 2), dtype=np.float64)
     Rm = np.empty_like(R)
-    _load().orc_interaction_self_fwd(_p(Z), _p(zm), B, F, d, _p(R), _p(Rm))
+    _load().orc_interaction_self_fwd(_p(Z), _p(zm), B, F, d, int(bool(bf16)), _p(R), _p(Rm))
     return R, Rm
 
 
-def interaction_self_bwd(Z, dR, zmag=None):
+def interaction_self_bwd(Z, dR, zmag=None, bf16: bool = False):
     Z = _c(Z, np.float64)
     B, F, d = Z.shape
     dR = _c(dR, np.float64)
     zm = None if zmag is None else _c(zmag, np.float64)
     dZ = np.empty((B, F, d), dtype=np.float64)
     dm = np.empty_like(dZ)
-    _load().orc_interaction_self_bwd(_p(Z), _p(zm), _p(dR), B, F, d, _p(dZ), _p(dm))
+    _load().orc_interaction_self_bwd(_p(Z), _p(zm), _p(dR), B, F, d, int(bool(bf16)), _p(dZ),
+                                     _p(dm))
     return dZ, dm
 
 

@@ -292,6 +292,78 @@ def test_interaction_bwd_adjoint_and_finite_differences():
         assert abs(fd - dZ[b, i, k]) < 1e-8
 
 
+def _torch_bf16(x):
+    """Nearest-even bf16 of float64 values through torch's own cast (fp64 -> bf16 directly,
+    one rounding), widened back exactly: an implementation independent of the oracle's."""
+    return torch.from_numpy(np.asarray(x, np.float64)).to(torch.bfloat16).double().numpy()
+
+
+def test_interaction_bf16_operands_against_torch_cast_and_einsum():
+    """The bf16-operand mode (workloads with bf16 tables: operands rounded to bf16, fp32
+    accumulation) equals the Gram matrix of torch-rounded Z, and its backward equals the
+    symmetric pair-gradient matrix of torch-rounded dP times torch-rounded Z, plus the dense
+    gradient unrounded; the dense part of R stays the unrounded z_0."""
+    rng = np.random.default_rng(21)
+    B, F, d = 4, 9, 24
+    P = F * (F - 1) // 2
+    Z = rng.standard_normal((B, F, d)) * np.exp(rng.uniform(-3, 3, (B, F, 1)))
+    dR = rng.standard_normal((B, d + P))
+    R, Rm = orc.interaction_fwd(Z, bf16=True)
+    Zb = _torch_bf16(Z)
+    assert not np.array_equal(Zb, Z)                       # the rounding is not a no-op here
+    G = np.einsum("bfd,bgd->bfg", Zb, Zb)
+    li, lj = np.tril_indices(F, -1)
+    np.testing.assert_allclose(R[:, d:], G[:, li, lj], rtol=1e-13, atol=1e-13)
+    np.testing.assert_array_equal(R[:, :d], Z[:, 0, :])
+    Gm = np.einsum("bfd,bgd->bfg", np.abs(Zb), np.abs(Zb))
+    np.testing.assert_allclose(Rm[:, d:], Gm[:, li, lj], rtol=1e-13)
+    # differs from the full-precision interaction by about the bf16 operand rounding
+    R64, Rm64 = orc.interaction_fwd(Z)
+    rel = np.abs(R - R64)[:, d:] / Rm64[:, d:]
+    assert rel.max() <= 2 * 2.0 ** -8 + 2.0 ** -16 and rel.max() > 1e-5
+    # backward: dZ = S Zb (+ dR_dense on slot 0), S symmetric with zero diagonal
+    dZ, dm = orc.interaction_bwd(Z, dR, bf16=True)
+    Pb = _torch_bf16(dR[:, d:])
+    S = np.zeros((B, F, F))
+    S[:, li, lj] = Pb
+    S[:, lj, li] = Pb
+    want = np.matmul(S, Zb)
+    want[:, 0, :] += dR[:, :d]
+    np.testing.assert_allclose(dZ, want, rtol=1e-12, atol=1e-12)
+    wm = np.matmul(np.abs(S), np.abs(Zb))
+    wm[:, 0, :] += np.abs(dR[:, :d])
+    np.testing.assert_allclose(dm, wm, rtol=1e-12)
+    # self-dot pairs: the Gram lower triangle with its diagonal, and 2 dP_ii on the diagonal
+    Ps = F * (F + 1) // 2
+    dRs = rng.standard_normal((B, d + Ps))
+    Rs, _ = orc.interaction_self_fwd(Z, bf16=True)
+    si, sj = np.tril_indices(F, 0)
+    np.testing.assert_allclose(Rs[:, d:], G[:, si, sj], rtol=1e-13, atol=1e-13)
+    dZs, _ = orc.interaction_self_bwd(Z, dRs, bf16=True)
+    Pbs = _torch_bf16(dRs[:, d:])
+    Ss = np.zeros((B, F, F))
+    Ss[:, si, sj] = Pbs
+    Ss[:, sj, si] = Pbs
+    Ss[:, np.arange(F), np.arange(F)] *= 2.0
+    wants = np.matmul(Ss, Zb)
+    wants[:, 0, :] += dRs[:, :d]
+    np.testing.assert_allclose(dZs, wants, rtol=1e-12, atol=1e-12)
+
+
+def test_interaction_bf16_mode_is_plain_mode_on_bf16_values():
+    """Operands that are already bf16 values are left alone: both modes agree bit for bit."""
+    rng = np.random.default_rng(22)
+    B, F, d = 3, 6, 16
+    Z = _torch_bf16(rng.standard_normal((B, F, d)))
+    dR = rng.standard_normal((B, d + F * (F - 1) // 2))
+    dR[:, d:] = _torch_bf16(dR[:, d:])
+    for fn, args in ((orc.interaction_fwd, (Z,)), (orc.interaction_bwd, (Z, dR))):
+        a, am = fn(*args)
+        b, bm = fn(*args, bf16=True)
+        np.testing.assert_array_equal(a, b)
+        np.testing.assert_array_equal(am, bm)
+
+
 # ----------------------------------------------------------------------------- backward
 def _bag_setup(seed=10, T=3, B=16, rows=(50, 80, 30), d=4):
     rng = np.random.default_rng(seed)
