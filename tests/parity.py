@@ -1,35 +1,164 @@
-"""Helpers of the parity tests: tolerance checks against the oracle's magnitude bounds.
+"""Helpers of the parity tests: error bounds derived from the arithmetic, and the checks.
 
-The bar: bit-exact for integer and index work; for floating point, element-wise
-|y_gpu - y_oracle| <= rtol * M with M the oracle's sum of |terms| (M = 0 means exact);
-rtol = 1e-5 for fp32 arithmetic, 1e-2 for bf16 storage or bf16 matrix-core operands.
+The bar: bit-exact for integer and index work.  For floating point an element passes when
+|y_gpu - y_oracle| <= eps * M, M the oracle's sum of |terms| (M = 0 means exact), and eps is
+derived below from how many roundings the kernel's arithmetic can put on a path.
+
+Notation (Higham, "Accuracy and Stability of Numerical Algorithms", 2nd ed., section 3.1 and
+chapter 4):
+  u    unit roundoff: U32 = 2^-24 for binary32, U16 = 2^-8 for bfloat16 (8 significand bits)
+  g_k  gamma_k = k u / (1 - k u): k successive roundings give a relative error of at most g_k.
+       A sum of n terms evaluated in ANY order (any binary tree of n leaves, depth <= n - 1)
+       errs by at most g_{n-1} * sum |x_i|; a dot product of n terms, each product exact
+       inside a fused multiply-add (or exact as bf16 x bf16 in fp32), by g_n * sum |x_i y_i|.
+  (+)  composition: errors e1, e2 on a path compose to (1 + e1)(1 + e2) - 1.
+
+Per-call bounds (both sides see the same inputs):
+  pooling            g_{L-1}, L the longest bag (fp32 accumulation; bf16 rows widen exactly)
+  dots, fp32         g_d (fused multiply-add chains and sums over d columns)
+  dots, bf16 MFMA    g_d against the oracle's bf16-operand mode (products exact in fp32)
+  dZ = S Z           g_F (F - 1 pair terms and the dense gradient); a bf16 store of dZ adds
+                     U16 * |dZ| (store_bound)
+  segment reduce     g_D, D the depth of the reduce-by-key tree (segreduce_depth), which
+                     does not grow with a segment's length
+  SGD store          sgd_store_bound: fl32(w - lr g) once (fp32 tables), then nearest-even
+                     to bf16 (bf16 tables: a double rounding), against the oracle's single
+                     rounding of the exact value
+
+Chained bounds (one step end to end against the oracle's own chain): each stage's input
+error enters its output through the stage's arithmetic (linear stages pass it through, the
+pair products take it from both factors) and composes with the stage's own roundings.
+`step_bounds` writes these out.
 """
 import numpy as np
 
-RTOL_F32 = 1e-5
-RTOL_BF16 = 1e-2
+RTOL_F32 = 1e-5          # the per-call figure for fp32 arithmetic
+RTOL_BF16 = 1e-2         # the per-call figure for bf16 storage / bf16 operands
+U32 = 2.0 ** -24
+U16 = 2.0 ** -8
+
+
+def gamma(k, u=U32):
+    k = max(int(k), 0)
+    return k * u / (1.0 - k * u)
+
+
+def compose(*eps):
+    r = 1.0
+    for e in eps:
+        r *= 1.0 + e
+    return r - 1.0
+
+
+def segreduce_depth(n, dim, bf16_grads):
+    """Most roundings on any path of the backward's reduce-by-key tree over n sorted
+    positions of rows of `dim` values.  A level sums a piece of at most KPS positions inside
+    a slot (KPS - 1 additions), then joins at most (slots - 1) following pieces of the same
+    row in order; the carries of a level form the next level's input, until one chunk of
+    slots * KPS positions is left.  slots = 256 / G with G = 16-byte vectors per row rounded
+    up to a power of two (at most 64); KPS = 6 for bf16 gradient rows, 4 for fp32."""
+    vecs = max(1, int(dim) // 4)
+    G = 1
+    while G < 64 and G < vecs:
+        G *= 2
+    slots = 256 // G
+    kps = 6 if bf16_grads else 4
+    chunk = slots * kps
+    levels = 1
+    blocks = -(-max(int(n), 1) // chunk)
+    while blocks > 1:
+        blocks = -(-(2 * blocks) // chunk)
+        levels += 1
+    return levels * ((kps - 1) + (slots - 1))
+
+
+def pool_eps(offsets, batch, num_tables):
+    """Per-bag bound g_{L-1} of the pooled sums, shaped [batch, num_tables, 1]: the kernels
+    add a bag's rows one after another within a share and join the shares' pieces in order,
+    so no path has more than L - 1 roundings."""
+    lens = np.diff(np.asarray(offsets, np.int64)).reshape(num_tables, batch).T
+    k = np.maximum(lens - 1, 0).astype(np.float64)
+    return (k * U32 / (1.0 - k * U32))[:, :, None]
+
+
+def store_bound(want, mag, eps, store_bf16):
+    """Element-wise bound of a value computed within eps * M in fp32 and stored as bf16
+    (nearest-even: a further U16 of the stored value) or kept in fp32."""
+    want = np.abs(np.asarray(want, np.float64))
+    mag = np.asarray(mag, np.float64)
+    if not store_bf16:
+        return eps * mag
+    return eps * mag * (1.0 + U16) + U16 * want
+
+
+def sgd_store_bound(new, gmag, lr, eps_g, table_bf16):
+    """Bound of |W'_gpu - W'_oracle| per element.  The oracle stores s1(x) with x = w - lr g
+    exact and s1 one rounding to the table type; the kernel stores s2(fl32(w - lr g~)) with
+    |g~ - g| <= eps_g * gmag (one fused multiply-add, then nearest-even for bf16)."""
+    s1 = U16 if table_bf16 else U32
+    s2 = (U16 + U32 + U16 * U32) if table_bf16 else U32
+    x = np.abs(np.asarray(new, np.float64)) / (1.0 - s1)
+    dg = float(lr) * eps_g * np.asarray(gmag, np.float64)
+    return dg + s2 * (x + dg) + s1 * x
+
+
+def step_bounds(max_bag, dim, F, n, compute_bf16, grad_bf16):
+    """Relative bounds (times the oracle's M) of one front-end step end to end:
+      Z  the pooled vectors; R the interaction output; dZ its gradient (in fp32 before any
+      bf16 store); g the row gradients (fp32; from bf16-stored dZ when grad_bf16)."""
+    eZ = gamma(max_bag - 1)
+    if compute_bf16:
+        d = compose(U16, eZ)                           # a bf16 factor against the exact z
+        eR = compose(d, d, gamma(dim))
+        edZ = compose(U16, d, gamma(F))                # bf16 dP and bf16 z, F terms
+    else:
+        eR = compose(eZ, eZ, gamma(dim))
+        edZ = compose(eZ, gamma(F))
+    edZ_in = compose(edZ, U16) if grad_bf16 else edZ   # what the segment reduce reads
+    eg = compose(edZ_in, gamma(segreduce_depth(n, dim, grad_bf16)))
+    return {"Z": eZ, "R": eR, "dZ": edZ, "dZ_stored": edZ_in, "g": eg}
+
+
+def _ratio(err, mag):
+    m = np.asarray(mag, np.float64)
+    return np.where(m > 0, err / np.where(m > 0, m, 1.0), np.where(err > 0, np.inf, 0.0))
 
 
 def assert_close(got, want, mag, rtol, what=""):
+    """|got - want| <= rtol * mag element-wise; prints the worst err/M against the bound."""
     got = np.asarray(got, dtype=np.float64)
     want = np.asarray(want, dtype=np.float64)
     mag = np.asarray(mag, dtype=np.float64)
     assert got.shape == want.shape, (what, got.shape, want.shape)
+    return assert_within(got, want, rtol * mag, what, mag=mag)
+
+
+def assert_within(got, want, bound, what="", mag=None):
+    """|got - want| <= bound element-wise (bound from the derivation above)."""
+    got = np.asarray(got, dtype=np.float64)
+    want = np.asarray(want, dtype=np.float64)
+    bound = np.broadcast_to(np.asarray(bound, dtype=np.float64), want.shape)
+    assert got.shape == want.shape, (what, got.shape, want.shape)
     assert np.all(np.isfinite(got)), "%s: non-finite GPU values" % what
     err = np.abs(got - want)
-    bound = rtol * mag
     bad = err > bound
+    used = float(np.max(_ratio(err, bound))) if err.size else 0.0
+    if mag is not None and err.size:
+        print("%s: worst err/M %.3g, bound/M %.3g (%.2f of the bound)" % (
+            what, float(np.max(_ratio(err, mag))), float(np.max(_ratio(bound, mag))), used),
+            flush=True)
+    elif err.size:
+        print("%s: %.2f of the bound at worst" % (what, used), flush=True)
     if bad.any():
         idx = np.argwhere(bad)[:5]
-        ratio = np.max(err / np.maximum(mag, 1e-300))
-        raise AssertionError("%s: %d of %d elements outside %g*M (worst err/M %.3g) at %s: got %s "
-                             "want %s M %s" % (what, int(bad.sum()), bad.size, rtol, ratio,
-                                               idx.tolist(), got[tuple(idx[0])],
-                                               want[tuple(idx[0])], mag[tuple(idx[0])]))
+        raise AssertionError("%s: %d of %d elements outside the bound (worst err/bound %.3g) at "
+                             "%s: got %s want %s bound %s" % (
+                                 what, int(bad.sum()), bad.size, used, idx.tolist(),
+                                 got[tuple(idx[0])], want[tuple(idx[0])], bound[tuple(idx[0])]))
+    return used
 
 
 def worst_ratio(got, want, mag):
     err = np.abs(np.asarray(got, np.float64) - want)
-    m = np.asarray(mag, np.float64)
-    r = np.where(m > 0, err / np.where(m > 0, m, 1), np.where(err > 0, np.inf, 0))
+    r = _ratio(err, mag)
     return float(r.max()) if r.size else 0.0

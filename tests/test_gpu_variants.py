@@ -12,7 +12,7 @@ import torch
 
 from oracle import oracle as orc
 from sparse_embedding_lookup_amd import ctr
-from tests.parity import RTOL_BF16, RTOL_F32, assert_close
+from tests.parity import RTOL_F32, assert_close, gamma
 from tests.test_gpu_parity import DEV, dev, host, say
 
 pytestmark = [pytest.mark.gpu,
@@ -41,8 +41,8 @@ def test_self_fwd_matches_oracle(compute, B, F, d):
     Z, _ = _inputs(B, F, d, d + P, 11)
     code = ctr.CTR_BF16 if compute == "bf16" else ctr.CTR_F32
     R = host(ctr.ctr_dot_interaction_self_fwd(dev(Z), code))
-    want, mag = orc.interaction_self_fwd(Z.astype(np.float64))
-    assert_close(R, want, mag, RTOL_BF16 if compute == "bf16" else RTOL_F32, "self fwd")
+    want, mag = orc.interaction_self_fwd(Z.astype(np.float64), bf16=compute == "bf16")
+    assert_close(R, want, mag, gamma(d), "self fwd")
     np.testing.assert_array_equal(R[:, :d], Z[:, 0, :])
 
 
@@ -53,8 +53,10 @@ def test_self_bwd_matches_oracle(compute, B, F, d):
     Z, dR = _inputs(B, F, d, d + P, 12)
     code = ctr.CTR_BF16 if compute == "bf16" else ctr.CTR_F32
     dZ = host(ctr.ctr_dot_interaction_self_bwd(dev(Z), dev(dR), code))
-    want, mag = orc.interaction_self_bwd(Z.astype(np.float64), dR.astype(np.float64))
-    assert_close(dZ, want, mag, RTOL_BF16 if compute == "bf16" else RTOL_F32, "self bwd")
+    want, mag = orc.interaction_self_bwd(Z.astype(np.float64), dR.astype(np.float64),
+                                         bf16=compute == "bf16")
+    # F pair terms (the self term included) and the dense gradient
+    assert_close(dZ, want, mag, gamma(F + 1), "self bwd")
 
 
 def test_self_strided_output_and_strict_unchanged():
@@ -65,7 +67,7 @@ def test_self_strided_output_and_strict_unchanged():
     ctr.ctr_dot_interaction_self_fwd(dev(Z), ctr.CTR_F32, big)
     got = host(big)
     want, mag = orc.interaction_self_fwd(Z.astype(np.float64))
-    assert_close(got[:, :d + P], want, mag, RTOL_F32, "strided self R")
+    assert_close(got[:, :d + P], want, mag, gamma(d), "strided self R")
     assert np.all(got[:, d + P:] == -7.0)
     # the strict entry point still writes F(F-1)/2 pairs
     Rs = host(ctr.ctr_dot_interaction_fwd(dev(Z), ctr.CTR_F32))
