@@ -30,7 +30,8 @@ cross-stream wait on this stack) stays off the steps.  "native" calls ctr_step_r
 step; "python" makes one binding call per stage (the pipelined schedule then replays the next
 batch's unique and the stages after the pooling kernel from captured graphs).
 
-    python bench.py [--config small|tiny|criteo|tensornet|large] [--steps K] [--warmup W]
+    python bench.py [--config large|small|tiny|criteo|tensornet|dictionary] [--steps K]
+                    [--warmup W]
                     [--schedule pipelined|serial] [--compare-serial]
                     [--launch native|python|graph]
 """
@@ -58,22 +59,36 @@ WORKLOAD_NAMES = {
 }
 
 
+def grad_elem_bytes(w):
+    """Bytes per gradient value the backward reads: the matrix-core interaction stores dZ in
+    bf16 (the step's gradient dtype for bf16 compute), everything else is fp32."""
+    return 2 if (w.interaction and w.compute == "bf16") else 4
+
+
 def compulsory_bytes(w, U, stage):
-    """The pooled gather's bytes with each distinct row read once (U rows instead of nnz)."""
-    assert stage == "embbag_fwd"
+    """The stage's bytes with each distinct row read once: the pooled gather reads U rows
+    instead of nnz; the fused backward reads each bag's gradient row once (T*B rows, or one
+    per occurrence without bags) instead of once per occurrence."""
     n, d = w.nnz, w.dim
+    rb = d * (2 if w.dtype == "bf16" else 4)
+    if stage == "embbag_bwd_sgd":
+        rows = w.num_tables * w.batch if w.interaction else n
+        return rows * d * grad_elem_bytes(w) + 8 * n + 2 * U * rb
+    assert stage == "embbag_fwd"
     if w.interaction:
-        rb = d * (2 if w.dtype == "bf16" else 4)
         nb = w.num_tables * w.batch
         return U * rb + 8 * n + 8 * (nb + 1) + 4 * nb * d
     return U * 4 * d + 4 * n + 8 * (n + 1) + 4 * n * d
 
 
 def stage_bytes(w, U):
-    """Algorithmic bytes moved by each stage (what the method must read and write)."""
+    """Algorithmic bytes moved by each stage (what the method must read and write).  The
+    fused backward + SGD counts every occurrence's gradient row (at the gradient's element
+    size), the occurrence's 8-byte index, and the read and write of each updated row."""
     n = w.nnz
     d = w.dim
     rb = d * (2 if w.dtype == "bf16" else 4)
+    sg = grad_elem_bytes(w)
     if w.interaction:
         B, T, F, P = w.batch, w.num_tables, w.F, w.P
         nb = T * B
@@ -82,9 +97,9 @@ def stage_bytes(w, U):
             "interaction_fwd": 4 * B * F * d + 4 * B * (d + P),
             "interaction_bwd": 4 * B * (d + P) + 8 * B * F * d,
             "unique": 8 * n + 8 * (nb + 1) + 4 * n + 4 * n + 12 * U + 4 * U,
-            "embbag_bwd": 4 * n * d + 8 * n + 4 * U * d,
+            "embbag_bwd": sg * n * d + 8 * n + 4 * U * d,
             "sparse_sgd": 2 * U * rb + 4 * U * d + 8 * U,
-            "embbag_bwd_sgd": 4 * n * d + 8 * n + 8 * U + 2 * U * rb,
+            "embbag_bwd_sgd": sg * n * d + 8 * n + 2 * U * rb,
         }
     return {
         "unique": 8 * n + 4 * n + 4 * n + 12 * U + 4 * U,
@@ -92,14 +107,21 @@ def stage_bytes(w, U):
         "embbag_fwd": n * 4 * d + 4 * n + 8 * (n + 1) + 4 * n * d,
         "embbag_bwd": 4 * n * d + 8 * n + 4 * U * d,
         "sparse_sgd": 2 * U * rb + 4 * U * d + 8 * U,
-        "embbag_bwd_sgd": 4 * n * d + 8 * n + 8 * U + 2 * U * rb,
+        "embbag_bwd_sgd": sg * n * d + 8 * n + 2 * U * rb,
     }
 
+
+KERNEL_NAMES = {
+    "embbag_fwd": "embbag_fwd_balanced_kernel (pooled gather)",
+    "embbag_bwd_sgd": "segreduce_kernel, level 0 (fused backward + sparse SGD)",
+}
 
 # Stages that are one kernel launch each (a roofline needs one kernel's duration), with the
 # kernel's name prefix and source file.
 SINGLE_KERNEL = {
     "embbag_fwd": ("embbag_fwd_", "embbag.hip"),
+    # the reduce-by-key level over every sorted position (its carry levels are short)
+    "embbag_bwd_sgd": ("segreduce_kernel<true", "segreduce.hip"),
     "interaction_fwd": ("interaction_fwd_", "interaction.hip"),
     "interaction_bwd": ("interaction_bwd_", "interaction.hip"),
     "sparse_sgd": ("sparse_sgd_kernel", "embbag.hip"),
@@ -315,9 +337,10 @@ def time_dlrm(fe, w, K: int):
 
 
 def measured_traffic(config: str, stage: str):
-    """HBM bytes per launch of the stage's kernel from the committed rocprofv3 counter runs
-    (FETCH_SIZE + WRITE_SIZE, each scaled by a plain copy of known size), or None when
-    there is no such run or the kernel's source changed since it was taken."""
+    """Bytes per launch that the stage's kernel moved between L2 and memory, from the
+    committed rocprofv3 counter runs (read requests counted by size, 32/64/128 bytes, and
+    write requests), or None when there is no such run or the kernel's source changed since
+    it was taken."""
     import hashlib
     path = os.path.join(ROOT, "profiles", "hbm_traffic_%s.json" % config)
     if not os.path.exists(path):
@@ -585,7 +608,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", default="small", choices=sorted(WORKLOAD_NAMES))
+    ap.add_argument("--config", default="large", choices=sorted(WORKLOAD_NAMES))
     ap.add_argument("--ids", default="zipf", choices=["zipf", "uniform"],
                     help="zipf: the workload's power-law IDs; uniform: the same shapes with "
                          "uniform IDs (the control where caches cannot help)")
@@ -725,13 +748,14 @@ def main():
                          for n in names}
         del flush, cold
     byts = stage_bytes(w, U)
-    # the roofline's kernel: the single-kernel stage that moves the most algorithmic bytes
-    # (the pooled gather on every workload); fixed by the workload, not by a timing
-    dominant = max((s for s in stage_ms if s in SINGLE_KERNEL), key=lambda s: byts[s])
+    # the roofline's kernel: the one that takes the most time per step, among the kernels
+    # whose launches the timing marks can bracket (ctr_step_run: the pooling kernel, or the
+    # backward's first reduce-by-key level, which carries nearly all of the backward's time)
+    markable = ("embbag_fwd", "embbag_bwd_sgd") if native else tuple(SINGLE_KERNEL)
+    dominant = max((s for s in stage_ms if s in markable), key=lambda s: stage_ms[s])
     if native:
-        # ctr_step_run brackets the pooling kernel with the timing events; on the Tiny batch
-        # (launch-bound, every kernel a few microseconds) another stage may move more bytes
-        dominant = "embbag_fwd"
+        fe.native().mark_stage = (ctr.CTR_MARK_BACKWARD if dominant == "embbag_bwd_sgd"
+                                  else ctr.CTR_MARK_POOLING)
         warm()
     elif pipelined:
         # the next batch's unique and the stages after the dominant kernel replay from captured
@@ -826,7 +850,9 @@ def main():
             print("[bench] CPU oracle of the MLPs", file=sys.stderr, flush=True)
             dlrm["cpu_baseline_mlp"] = cpu_baseline_mlp(w, min(args.cpu_seconds, 8.0))
 
-    step_bytes = sum(byts.values())
+    comp = (compulsory_bytes(w, U, dominant) if dominant in ("embbag_fwd", "embbag_bwd_sgd")
+            else None)
+    step_bytes = sum(byts[k] for k in stage_ms)          # the stages the step runs
     value = w.nnz / (ms_step * 1e-3)
     achieved = byts[dominant] / (dom_ms * 1e-3) / 1e9
     out = {
@@ -873,20 +899,29 @@ def main():
                           if stage_ms_cold else None),
         "variants": variants,
         "dlrm": dlrm,
-        "roofline": {"kernel": dominant, "bound": "hbm", "achieved": achieved,
+        "roofline": {"kernel": KERNEL_NAMES.get(dominant, dominant), "stage": dominant,
+                     "bound": "hbm", "achieved": achieved,
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
                      "traffic": measured_traffic(
                          args.config if args.ids == "zipf" else args.config + "_" + args.ids,
                          dominant),
-                     "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE+WRITE_SIZE)",
+                     "traffic_unit": "bytes per launch leaving L2 toward memory (rocprofv3 TCC_EA0 "
+                                     "read requests by size + write requests)",
                      "bytes_per_launch": byts[dominant],
                      "avg_launch_ms": dom_ms,
-                     "compulsory_bytes": compulsory_bytes(w, U, dominant),
-                     "compulsory_frac": compulsory_bytes(w, U, dominant) / (dom_ms * 1e-3) / 1e9
-                     / HBM_PEAK_GBPS,
+                     "compulsory_bytes": comp,
+                     "compulsory_frac": (comp / (dom_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS
+                                         if comp else None),
                      # the kernel alone with cold caches (per-stage timing after a flush)
                      "cold_frac": (byts[dominant] / (stage_ms_cold[dominant] * 1e-3) / 1e9
                                    / HBM_PEAK_GBPS if stage_ms_cold else None)},
+        # the pooled gather alone (each stage bracketed by itself before the timed steps):
+        # the gather figure, beside the roofline of the kernel that takes the most time
+        "pooling": {"ms": round(stage_ms["embbag_fwd"], 5), "bytes": byts["embbag_fwd"],
+                    "frac": byts["embbag_fwd"] / (stage_ms["embbag_fwd"] * 1e-3) / 1e9
+                    / HBM_PEAK_GBPS,
+                    "compulsory_frac": compulsory_bytes(w, U, "embbag_fwd")
+                    / (stage_ms["embbag_fwd"] * 1e-3) / 1e9 / HBM_PEAK_GBPS},
     }
     if not args.no_cpu:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)

@@ -417,6 +417,10 @@ enum {
   CTR_SCHEDULE_PIPELINED_EARLY = 2,
   CTR_SCHEDULE_PIPELINED_OVERLAP = 3
 };
+/* Where ctr_step_run's timing marks go: around the pooling kernel, or around the backward's
+ * first reduce-by-key kernel (the one over every sorted position; the carry levels after it
+ * are outside the marks). */
+enum { CTR_MARK_POOLING = 0, CTR_MARK_BACKWARD = 1 };
 
 typedef struct {
   int32_t kind;
@@ -459,6 +463,7 @@ typedef struct {
                                      CTR_BF16; dZ then holds bf16 [batch, F, dim]) */
   void* ws_unique2;               /* ctr_step_run_deep: the second side stream's unique */
   size_t ws_unique2_bytes;        /*   workspace (two uniques run at once) */
+  int32_t mark_stage;             /* CTR_MARK_POOLING (0) or CTR_MARK_BACKWARD (1) */
 } ctr_step_t;
 
 /*
@@ -483,6 +488,7 @@ typedef struct {
  *                           record nothing else into them.
  * fork_event / join_event: caller-created events (required with a side stream); mark_begin /
  * mark_end: optional events recorded on main_stream right before and after the pooling
+ * kernel, or, with step->mark_stage == CTR_MARK_BACKWARD, the backward's first reduce-by-key
  * kernel.  Under stream capture (graph building) the marks become event-record nodes of the
  * graph, so that each replay leaves them timed.  Returns the first failing call's status;
  * the calls before it stay enqueued.

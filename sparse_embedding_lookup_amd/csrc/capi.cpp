@@ -56,6 +56,26 @@ int32_t check_table(const void* table, int32_t dtype, int64_t total_rows, int32_
 
 namespace ctr {
 int32_t set_error(int32_t code, const char* msg) { return fail(code, "%s", msg); }
+
+hipError_t record_mark(void* ev, hipStream_t s) {
+  if (!ev) return hipSuccess;
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  hipError_t e = hipStreamIsCapturing(s, &cs);
+  if (e != hipSuccess) return e;
+  if (cs != hipStreamCaptureStatusActive) return hipEventRecord(static_cast<hipEvent_t>(ev), s);
+  hipStreamCaptureStatus st;
+  unsigned long long id;
+  hipGraph_t g;
+  const hipGraphNode_t* deps;
+  size_t ndeps;
+  hipGraphNode_t node;
+  e = hipStreamGetCaptureInfo_v2(s, &st, &id, &g, &deps, &ndeps);
+  if (e == hipSuccess)
+    e = hipGraphAddEventRecordNode(&node, g, deps, ndeps, static_cast<hipEvent_t>(ev));
+  if (e == hipSuccess)
+    e = hipStreamUpdateCaptureDependencies(s, &node, 1, hipStreamSetCaptureDependencies);
+  return e;
+}
 }  // namespace ctr
 
 extern "C" {
@@ -221,7 +241,8 @@ static int32_t embbag_bwd_sgd_common(const void* grad, bool grad_bf16, int64_t g
                                      void* table, int32_t dtype, int64_t total_rows, int32_t dim,
                                      const int64_t* uniq, float lr, float* row_grads,
                                      void* workspace, size_t* workspace_bytes, bool stochastic,
-                                     uint64_t seed, void* stream, const char* name) {
+                                     uint64_t seed, void* stream, const char* name,
+                                     void* l0_begin = nullptr, void* l0_end = nullptr) {
   g_msg[0] = 0;
   if (!workspace_bytes) return fail(CTR_ERR_INVALID_ARGUMENT, "workspace_bytes is NULL");
   if (table) {
@@ -271,9 +292,41 @@ static int32_t embbag_bwd_sgd_common(const void* grad, bool grad_bf16, int64_t g
                                            offsets, batch, num_tables, dim, nnz, nullptr,
                                            nullptr, reinterpret_cast<const int4*>(sorted_src),
                                            num_unique, row_grads, table, mode, total_rows, uniq,
-                                           lr, seed, workspace, (hipStream_t)stream),
+                                           lr, seed, workspace, (hipStream_t)stream, l0_begin,
+                                           l0_end),
                     name);
 }
+
+}  // extern "C"
+
+namespace ctr {
+// ctr_embbag_bwd_sgd_ex with timing marks recorded right before and after the first
+// reduce-by-key kernel (the native step runner's marks).
+int32_t embbag_bwd_sgd_marked(const void* grad, int32_t grad_dtype, int64_t grad_stride_b,
+                              int64_t grad_stride_t, const int64_t* offsets, int64_t batch,
+                              int32_t num_tables, int64_t nnz, const int32_t* sorted_src,
+                              const int32_t* num_unique, void* table, int32_t dtype,
+                              int64_t total_rows, int32_t dim, const int64_t* uniq, float lr,
+                              int32_t rounding, uint64_t seed, float* row_grads, void* workspace,
+                              size_t* workspace_bytes, void* stream, void* l0_begin,
+                              void* l0_end) {
+  if (grad_dtype != CTR_F32 && grad_dtype != CTR_BF16) {
+    g_msg[0] = 0;
+    return fail(CTR_ERR_INVALID_ARGUMENT, "grad_dtype %d is not CTR_F32 or CTR_BF16", grad_dtype);
+  }
+  if (rounding != CTR_ROUND_NEAREST && rounding != CTR_ROUND_STOCHASTIC) {
+    g_msg[0] = 0;
+    return fail(CTR_ERR_INVALID_ARGUMENT, "unknown rounding %d", rounding);
+  }
+  return embbag_bwd_sgd_common(grad, grad_dtype == CTR_BF16, grad_stride_b, grad_stride_t,
+                               offsets, batch, num_tables, nnz, sorted_src, num_unique, table,
+                               dtype, total_rows, dim, uniq, lr, row_grads, workspace,
+                               workspace_bytes, rounding == CTR_ROUND_STOCHASTIC, seed, stream,
+                               "ctr_step_run (backward)", l0_begin, l0_end);
+}
+}  // namespace ctr
+
+extern "C" {
 
 int32_t ctr_embbag_bwd_sgd_ex(const void* grad, int32_t grad_dtype, int64_t grad_stride_b,
                               int64_t grad_stride_t, const int64_t* offsets, int64_t batch,

@@ -110,6 +110,11 @@ inline RowGeom row_geom(int64_t vecs) {
 // Records the thread's ctr_last_error text and returns code (capi.cpp).
 int32_t set_error(int32_t code, const char* msg);
 
+// Records timing event `ev` (nothing when NULL) on stream s.  Under stream capture it adds an
+// event-record node after the stream's current capture dependencies, which becomes their
+// only one: a recorded event cannot be timed after a capture, such a node can (capi.cpp).
+hipError_t record_mark(void* ev, hipStream_t s);
+
 }  // namespace ctr
 
 #include "ctr_launch.h"

@@ -46,7 +46,18 @@ hipError_t launch_embbag_bwd(const void* grad, bool grad_bf16, int64_t sb, int64
                              const int32_t* perm, const int32_t* inverse, const int4* sorted_src,
                              const int32_t* num_unique, float* row_grads, void* table,
                              int sgd_mode, int64_t total_rows, const int64_t* uniq, float lr,
-                             uint64_t seed, void* workspace, hipStream_t s);
+                             uint64_t seed, void* workspace, hipStream_t s,
+                             void* l0_begin = nullptr, void* l0_end = nullptr);
+// The fused backward + SGD entry (ctr_embbag_bwd_sgd_ex) with timing marks around its first
+// reduce-by-key kernel (capi.cpp).
+int32_t embbag_bwd_sgd_marked(const void* grad, int32_t grad_dtype, int64_t grad_stride_b,
+                              int64_t grad_stride_t, const int64_t* offsets, int64_t batch,
+                              int32_t num_tables, int64_t nnz, const int32_t* sorted_src,
+                              const int32_t* num_unique, void* table, int32_t dtype,
+                              int64_t total_rows, int32_t dim, const int64_t* uniq, float lr,
+                              int32_t rounding, uint64_t seed, float* row_grads, void* workspace,
+                              size_t* workspace_bytes, void* stream, void* l0_begin,
+                              void* l0_end);
 
 // dict.hip
 hipError_t launch_dict_build(const int64_t* keys, const int32_t* rows, const int32_t* hot_slots,

@@ -691,8 +691,11 @@ size_t embbag_bwd_workspace_bytes(int64_t nnz, int dim) { return carve(nullptr, 
   } while (0)
 
 template <int MODE, typename L0S>
-static void segreduce_levels(const L0S& s0, int64_t nnz, int dim, float* row_grads,
-                             const SgdTarget& sgd, BwdWs& w, hipStream_t s) {
+static hipError_t segreduce_levels(const L0S& s0, int64_t nnz, int dim, float* row_grads,
+                                   const SgdTarget& sgd, BwdWs& w, hipStream_t s, void* l0_begin,
+                                   void* l0_end) {
+  hipError_t e = record_mark(l0_begin, s);
+  if (e != hipSuccess) return e;
   const RowGeom rg = row_geom(dim / 4);
   constexpr int KPS = slot_depth<L0S::kBf16>();
   const int64_t chunk = chunk_positions(dim, KPS);
@@ -703,7 +706,8 @@ static void segreduce_levels(const L0S& s0, int64_t nnz, int dim, float* row_gra
     segreduce_kernel<true, G, VPL, MODE, KPS, L0S><<<(unsigned)blocks, kThreads, 0, s>>>(
         s0, len, dim, nnz, row_grads, sgd, blocks > 1 ? w.ckeys[cur] : nullptr, w.crows[cur],
         w.ticket, nullptr);
-    while (blocks > 1) {
+    e = record_mark(l0_end, s);
+    while (e == hipSuccess && blocks > 1) {
       len = 2 * blocks;
       blocks = (len + chunk - 1) / chunk;
       LnSource sn{w.ckeys[cur], w.crows[cur], dim};
@@ -716,6 +720,7 @@ static void segreduce_levels(const L0S& s0, int64_t nnz, int dim, float* row_gra
       if (fold) break;
     }
   });
+  return e;
 }
 
 hipError_t launch_embbag_bwd(const void* grad, bool grad_bf16, int64_t sb, int64_t st,
@@ -724,9 +729,13 @@ hipError_t launch_embbag_bwd(const void* grad, bool grad_bf16, int64_t sb, int64
                              const int32_t* perm, const int32_t* inverse, const int4* sorted_src,
                              const int32_t* num_unique, float* row_grads, void* table,
                              int sgd_mode, int64_t total_rows, const int64_t* uniq, float lr,
-                             uint64_t seed, void* workspace, hipStream_t s) {
+                             uint64_t seed, void* workspace, hipStream_t s, void* l0_begin,
+                             void* l0_end) {
   (void)num_unique;
-  if (nnz == 0) return hipSuccess;
+  if (nnz == 0) {                          // nothing to reduce; the marks still bracket it
+    const hipError_t e = record_mark(l0_begin, s);
+    return e == hipSuccess ? record_mark(l0_end, s) : e;
+  }
   BwdWs w = carve(workspace, nnz, dim);
   const int64_t num_bags = (int64_t)num_tables * batch;
 
@@ -746,18 +755,16 @@ hipError_t launch_embbag_bwd(const void* grad, bool grad_bf16, int64_t sb, int64
   auto levels = [&](const auto& s0) {
     using S0 = std::decay_t<decltype(s0)>;
     if (sgd_mode == 1)
-      segreduce_levels<1, S0>(s0, nnz, dim, row_grads, sgd, w, s);
-    else if (sgd_mode == 2)
-      segreduce_levels<2, S0>(s0, nnz, dim, row_grads, sgd, w, s);
-    else if (sgd_mode == 3)
-      segreduce_levels<3, S0>(s0, nnz, dim, row_grads, sgd, w, s);
-    else
-      segreduce_levels<0, S0>(s0, nnz, dim, row_grads, sgd, w, s);
+      return segreduce_levels<1, S0>(s0, nnz, dim, row_grads, sgd, w, s, l0_begin, l0_end);
+    if (sgd_mode == 2)
+      return segreduce_levels<2, S0>(s0, nnz, dim, row_grads, sgd, w, s, l0_begin, l0_end);
+    if (sgd_mode == 3)
+      return segreduce_levels<3, S0>(s0, nnz, dim, row_grads, sgd, w, s, l0_begin, l0_end);
+    return segreduce_levels<0, S0>(s0, nnz, dim, row_grads, sgd, w, s, l0_begin, l0_end);
   };
-  if (grad_bf16)
-    levels(L0SourceB{src, grad, sb, st, batch, num_bags});
-  else
-    levels(L0Source{src, grad, sb, st, batch, num_bags});
+  const hipError_t e = grad_bf16 ? levels(L0SourceB{src, grad, sb, st, batch, num_bags})
+                                 : levels(L0Source{src, grad, sb, st, batch, num_bags});
+  if (e != hipSuccess) return e;
   return hipGetLastError();
 }
 

@@ -1,6 +1,6 @@
 // step.cpp -- one training step of the sparse front end enqueued from native code: every
 // call of the path, the fork and join of the unique's side stream, and optional timing
-// events around the pooling kernel, in one C call (the per-call cost of an interpreter
+// events around the pooling kernel or the backward's first kernel, in one C call (the per-call cost of an interpreter
 // would otherwise exceed the GPU time of a small batch).
 //
 // The step is the chain the pages describe: the batch's IDs deduplicated into contiguous
@@ -24,26 +24,9 @@ int32_t record(void* ev, hipStream_t s) {
   return e == hipSuccess ? CTR_OK : ctr::set_error(CTR_ERR_HIP, hipGetErrorString(e));
 }
 
-// A timing mark.  Under stream capture a recorded event cannot be timed afterwards, but an
-// event-record node added to the capture can: the node goes after the stream's current
-// capture dependencies and becomes the only one.
+// A timing mark (capture-aware: see ctr::record_mark).
 int32_t mark(void* ev, hipStream_t s) {
-  if (!ev) return CTR_OK;
-  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
-  hipError_t e = hipStreamIsCapturing(s, &cs);
-  if (e != hipSuccess) return ctr::set_error(CTR_ERR_HIP, hipGetErrorString(e));
-  if (cs != hipStreamCaptureStatusActive) return record(ev, s);
-  hipStreamCaptureStatus st;
-  unsigned long long id;
-  hipGraph_t g;
-  const hipGraphNode_t* deps;
-  size_t ndeps;
-  hipGraphNode_t node;
-  e = hipStreamGetCaptureInfo_v2(s, &st, &id, &g, &deps, &ndeps);
-  if (e == hipSuccess)
-    e = hipGraphAddEventRecordNode(&node, g, deps, ndeps, static_cast<hipEvent_t>(ev));
-  if (e == hipSuccess)
-    e = hipStreamUpdateCaptureDependencies(s, &node, 1, hipStreamSetCaptureDependencies);
+  const hipError_t e = ctr::record_mark(ev, s);
   return e == hipSuccess ? CTR_OK : ctr::set_error(CTR_ERR_HIP, hipGetErrorString(e));
 }
 
@@ -73,8 +56,10 @@ int32_t unique_into(const ctr_step_t* d, int set, void* stream, int ws = 0) {
 }
 
 // The stages before the unique may fork (pooling, and for the batch-matrix step the gather).
+// The timing marks bracket the pooling kernel unless the descriptor puts them on the backward.
 int32_t forward_part(const ctr_step_t* d, int set, hipStream_t s, void* mark_begin,
                      void* mark_end) {
+  if (d->mark_stage != CTR_MARK_POOLING) mark_begin = mark_end = nullptr;
   if (d->kind == CTR_STEP_POOLED_INTERACTION) {
     const int64_t F = (int64_t)d->num_tables + 1;
     CTR_TRY(mark(mark_begin, s));
@@ -101,8 +86,11 @@ int32_t interaction_part(const ctr_step_t* d, hipStream_t s) {
                                     (int32_t)F, d->dim, d->compute, 0, d->grad_dtype, d->dZ, s);
 }
 
-// The backward with the SGD update of the touched rows.
-int32_t sgd_part(const ctr_step_t* d, int set, int64_t k, hipStream_t s) {
+// The backward with the SGD update of the touched rows; with mark_stage CTR_MARK_BACKWARD the
+// timing marks bracket its first reduce-by-key kernel (over every sorted position).
+int32_t sgd_part(const ctr_step_t* d, int set, int64_t k, hipStream_t s, void* mark_begin,
+                 void* mark_end) {
+  if (d->mark_stage != CTR_MARK_BACKWARD) mark_begin = mark_end = nullptr;
   const int64_t F = (int64_t)d->num_tables + 1;
   size_t wsb = d->ws_bwd_bytes;
   const bool pooled = d->kind == CTR_STEP_POOLED_INTERACTION;
@@ -117,11 +105,11 @@ int32_t sgd_part(const ctr_step_t* d, int set, int64_t k, hipStream_t s) {
   const int64_t batch = pooled ? d->batch : d->nnz;
   const int32_t tables = pooled ? d->num_tables : 1;
   const bool sr = d->rounding == CTR_ROUND_STOCHASTIC;
-  return ctr_embbag_bwd_sgd_ex(grad, gdt, sb, st, d->offsets, batch, tables, d->nnz,
-                               d->sorted_src[set], d->num_unique[set], d->table, d->dtype,
-                               d->total_rows, d->dim, d->uniq[set], d->lr, d->rounding,
-                               sr ? ctr_sr_step_seed(d->sr_seed, k) : 0, d->row_grads, d->ws_bwd,
-                               &wsb, s);
+  return ctr::embbag_bwd_sgd_marked(grad, gdt, sb, st, d->offsets, batch, tables, d->nnz,
+                                    d->sorted_src[set], d->num_unique[set], d->table, d->dtype,
+                                    d->total_rows, d->dim, d->uniq[set], d->lr, d->rounding,
+                                    sr ? ctr_sr_step_seed(d->sr_seed, k) : 0, d->row_grads,
+                                    d->ws_bwd, &wsb, s, mark_begin, mark_end);
 }
 
 }  // namespace
@@ -146,6 +134,8 @@ int32_t ctr_step_run_deep(const ctr_step_t* d, int64_t k, void* main_stream, voi
   if (d->rounding != CTR_ROUND_NEAREST && d->rounding != CTR_ROUND_STOCHASTIC)
     return invalid("unknown rounding");
   if (d->grad_dtype != CTR_F32 && d->grad_dtype != CTR_BF16) return invalid("unknown grad_dtype");
+  if (d->mark_stage != CTR_MARK_POOLING && d->mark_stage != CTR_MARK_BACKWARD)
+    return invalid("unknown mark_stage");
   if (!side_stream0 || !side_stream1 || !events) return invalid("two side streams and six events are required");
   for (int i = 0; i < 6; ++i)
     if (!events[i]) return invalid("two side streams and six events are required");
@@ -168,7 +158,7 @@ int32_t ctr_step_run_deep(const ctr_step_t* d, int64_t k, void* main_stream, voi
   // two uniques can run at once, one per side stream: each stream has its own workspace
   CTR_TRY(unique_into(d, ahead, side, (int)(k & 1)));
   CTR_TRY(record(udone[ahead], side));
-  CTR_TRY(sgd_part(d, cur, k, s));
+  CTR_TRY(sgd_part(d, cur, k, s, mark_begin, mark_end));
   return record(bdone[cur], s);
 }
 
@@ -182,6 +172,8 @@ int32_t ctr_step_run(const ctr_step_t* d, int64_t k, int32_t schedule, void* mai
   if (d->rounding != CTR_ROUND_NEAREST && d->rounding != CTR_ROUND_STOCHASTIC)
     return invalid("unknown rounding");
   if (d->grad_dtype != CTR_F32 && d->grad_dtype != CTR_BF16) return invalid("unknown grad_dtype");
+  if (d->mark_stage != CTR_MARK_POOLING && d->mark_stage != CTR_MARK_BACKWARD)
+    return invalid("unknown mark_stage");
   if (schedule < CTR_SCHEDULE_SERIAL || schedule > CTR_SCHEDULE_PIPELINED_OVERLAP)
     return invalid("unknown schedule");
   if (side_stream && (!fork_event || !join_event))
@@ -206,7 +198,7 @@ int32_t ctr_step_run(const ctr_step_t* d, int64_t k, int32_t schedule, void* mai
     CTR_TRY(forward_part(d, 0, s, mark_begin, mark_end));
     CTR_TRY(interaction_part(d, s));
     if (fork) CTR_TRY(wait(s, join_event));
-    return sgd_part(d, 0, k, s);
+    return sgd_part(d, 0, k, s, mark_begin, mark_end);
   }
   const int cur = (int)(k & 1), nxt = cur ^ 1;
   if (schedule == CTR_SCHEDULE_PIPELINED_OVERLAP) {
@@ -221,7 +213,7 @@ int32_t ctr_step_run(const ctr_step_t* d, int64_t k, int32_t schedule, void* mai
     CTR_TRY(wait(side, fork_event));
     CTR_TRY(unique_into(d, nxt, side));
     CTR_TRY(record(join_event, side));
-    CTR_TRY(sgd_part(d, cur, k, s));
+    CTR_TRY(sgd_part(d, cur, k, s, mark_begin, mark_end));
     return record(fork_event, s);
   }
   // pipelined: batch k uses set k % 2 (filled during step k-1, or by ctr_step_unique before
@@ -235,7 +227,7 @@ int32_t ctr_step_run(const ctr_step_t* d, int64_t k, int32_t schedule, void* mai
   CTR_TRY(record(join_event, side));
   if (early) CTR_TRY(forward_part(d, cur, s, mark_begin, mark_end));
   CTR_TRY(interaction_part(d, s));
-  CTR_TRY(sgd_part(d, cur, k, s));
+  CTR_TRY(sgd_part(d, cur, k, s, mark_begin, mark_end));
   return wait(s, join_event);
 }
 

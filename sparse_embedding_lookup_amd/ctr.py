@@ -35,6 +35,7 @@ CTR_STEP_POOLED_INTERACTION, CTR_STEP_BATCH_MATRIX = 0, 1
 CTR_SCHEDULE_SERIAL, CTR_SCHEDULE_PIPELINED, CTR_SCHEDULE_PIPELINED_EARLY = 0, 1, 2
 CTR_SCHEDULE_PIPELINED_OVERLAP = 3
 CTR_ROUND_NEAREST, CTR_ROUND_STOCHASTIC = 0, 1
+CTR_MARK_POOLING, CTR_MARK_BACKWARD = 0, 1
 
 
 class CtrStep(ctypes.Structure):
@@ -52,7 +53,8 @@ class CtrStep(ctypes.Structure):
                 ("num_unique", _P * 3), ("perm", _P * 3), ("seg_offsets", _P * 3),
                 ("sorted_src", _P * 3), ("rounding", ctypes.c_int32),
                 ("sr_seed", ctypes.c_uint64), ("grad_dtype", ctypes.c_int32),
-                ("ws_unique2", _P), ("ws_unique2_bytes", ctypes.c_size_t)]
+                ("ws_unique2", _P), ("ws_unique2_bytes", ctypes.c_size_t),
+                ("mark_stage", ctypes.c_int32)]
 
 _lib = None
 
