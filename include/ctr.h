@@ -182,6 +182,31 @@ int32_t ctr_embbag_bwd_sgd_sr(const float* grad, int64_t grad_stride_b, int64_t 
                               void* workspace, size_t* workspace_bytes, void* stream);
 
 /*
+ * ctr_embbag_bwd_sgd_noalloc -- ctr_embbag_bwd_sgd_ex without a workspace, for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  Same arguments, kernels and results (bit for bit) as
+ * ctr_embbag_bwd_sgd_ex; sorted_src is required.  The reduce-by-key carries and the
+ * finisher's ticket live in a device array of ctr_noalloc_scratch_capacity() bytes (64 MiB)
+ * that the library holds on each GPU it runs on until the process ends, found once per device
+ * on the first call there; the call allocates and frees nothing.  A batch whose carries need
+ * more (ctr_embbag_bwd_noalloc_scratch_bytes(nnz, dim) above the capacity) returns
+ * CTR_ERR_UNSUPPORTED before any launch: e.g. dim 128 with bf16 gradients holds about 3e6
+ * occurrences.  Every call on a GPU shares that GPU's array, so calls that overlap on one GPU
+ * (two streams, two threads) race: serialise them.
+ */
+int32_t ctr_embbag_bwd_sgd_noalloc(const void* grad, int32_t grad_dtype, int64_t grad_stride_b,
+                                   int64_t grad_stride_t, const int64_t* offsets, int64_t batch,
+                                   int32_t num_tables, int64_t nnz, const int32_t* sorted_src,
+                                   const int32_t* num_unique, void* table, int32_t dtype,
+                                   int64_t total_rows, int32_t dim, const int64_t* uniq, float lr,
+                                   int32_t rounding, uint64_t seed, float* row_grads,
+                                   void* stream);
+/* Scratch bytes ctr_embbag_bwd_sgd_noalloc needs for nnz occurrences of dim-wide rows
+ * ((size_t)-1 for a bad size), and the capacity it has. */
+size_t ctr_embbag_bwd_noalloc_scratch_bytes(int64_t nnz, int32_t dim);
+size_t ctr_noalloc_scratch_capacity(void);
+
+/*
  * ctr_embbag_bwd_sgd_ex -- the backward of the pooling from sorted_src, in general form:
  *   grad: grad_dtype elements, CTR_F32 or CTR_BF16 (widened exactly; sums stay fp32),
  *         8-byte aligned for bf16, 16-byte for fp32;

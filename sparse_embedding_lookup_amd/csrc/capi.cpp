@@ -242,9 +242,11 @@ static int32_t embbag_bwd_sgd_common(const void* grad, bool grad_bf16, int64_t g
                                      const int64_t* uniq, float lr, float* row_grads,
                                      void* workspace, size_t* workspace_bytes, bool stochastic,
                                      uint64_t seed, void* stream, const char* name,
-                                     void* l0_begin = nullptr, void* l0_end = nullptr) {
+                                     void* l0_begin = nullptr, void* l0_end = nullptr,
+                                     bool noalloc = false) {
   g_msg[0] = 0;
-  if (!workspace_bytes) return fail(CTR_ERR_INVALID_ARGUMENT, "workspace_bytes is NULL");
+  if (!noalloc && !workspace_bytes)
+    return fail(CTR_ERR_INVALID_ARGUMENT, "workspace_bytes is NULL");
   if (table) {
     int32_t st = check_table(table, dtype, total_rows, dim);
     if (st) return st;
@@ -262,13 +264,22 @@ static int32_t embbag_bwd_sgd_common(const void* grad, bool grad_bf16, int64_t g
     return fail(CTR_ERR_INVALID_ARGUMENT, "bad batch");
   if (nnz > 0 && batch == 0)
     return fail(CTR_ERR_INVALID_ARGUMENT, "nnz > 0 needs at least one bag");
-  const size_t need = ctr::embbag_bwd_workspace_bytes(nnz, dim);
-  if (!workspace) {
-    *workspace_bytes = need;
-    return CTR_OK;
+  if (noalloc) {
+    const size_t need = ctr::embbag_bwd_noalloc_bytes(nnz, dim);
+    if (need > ctr::kNoallocScratchBytes)
+      return fail(CTR_ERR_UNSUPPORTED,
+                  "nnz %lld, dim %d need %zu bytes of scratch, above the %zu of %s",
+                  (long long)nnz, dim, need, ctr::kNoallocScratchBytes, name);
+  } else {
+    const size_t need = ctr::embbag_bwd_workspace_bytes(nnz, dim);
+    if (!workspace) {
+      *workspace_bytes = need;
+      return CTR_OK;
+    }
+    if (*workspace_bytes < need)
+      return fail(CTR_ERR_WORKSPACE_TOO_SMALL, "workspace %zu < %zu bytes", *workspace_bytes,
+                  need);
   }
-  if (*workspace_bytes < need)
-    return fail(CTR_ERR_WORKSPACE_TOO_SMALL, "workspace %zu < %zu bytes", *workspace_bytes, need);
   if (!offsets || !num_unique) return fail(CTR_ERR_INVALID_ARGUMENT, "offsets and num_unique are required");
   if (nnz > 0 && (!grad || !sorted_src || (table && !uniq)))
     return fail(CTR_ERR_INVALID_ARGUMENT, "grad, sorted_src and uniq are required");
@@ -286,8 +297,16 @@ static int32_t embbag_bwd_sgd_common(const void* grad, bool grad_bf16, int64_t g
                 grad_bf16 ? 8 : 16);
   if (reinterpret_cast<uintptr_t>(sorted_src) & 15u)
     return fail(CTR_ERR_UNSUPPORTED, "sorted_src is not 16-byte aligned");
-  if (!aligned16(workspace)) return fail(CTR_ERR_UNSUPPORTED, "workspace is not 16-byte aligned");
+  if (!noalloc && !aligned16(workspace))
+    return fail(CTR_ERR_UNSUPPORTED, "workspace is not 16-byte aligned");
   const int mode = !table ? 0 : dtype == CTR_BF16 ? (stochastic ? 3 : 2) : 1;
+  if (noalloc)
+    return hip_status(ctr::launch_embbag_bwd_noalloc(
+                          grad, grad_bf16, grad_stride_b, grad_stride_t, offsets, batch,
+                          num_tables, dim, nnz, reinterpret_cast<const int4*>(sorted_src),
+                          row_grads, table, mode, total_rows, uniq, lr, seed,
+                          (hipStream_t)stream),
+                      name);
   return hip_status(ctr::launch_embbag_bwd(grad, grad_bf16, grad_stride_b, grad_stride_t,
                                            offsets, batch, num_tables, dim, nnz, nullptr,
                                            nullptr, reinterpret_cast<const int4*>(sorted_src),
@@ -349,6 +368,35 @@ int32_t ctr_embbag_bwd_sgd_ex(const void* grad, int32_t grad_dtype, int64_t grad
                                workspace_bytes, rounding == CTR_ROUND_STOCHASTIC, seed, stream,
                                "ctr_embbag_bwd_sgd_ex");
 }
+
+int32_t ctr_embbag_bwd_sgd_noalloc(const void* grad, int32_t grad_dtype, int64_t grad_stride_b,
+                                   int64_t grad_stride_t, const int64_t* offsets, int64_t batch,
+                                   int32_t num_tables, int64_t nnz, const int32_t* sorted_src,
+                                   const int32_t* num_unique, void* table, int32_t dtype,
+                                   int64_t total_rows, int32_t dim, const int64_t* uniq, float lr,
+                                   int32_t rounding, uint64_t seed, float* row_grads,
+                                   void* stream) {
+  if (grad_dtype != CTR_F32 && grad_dtype != CTR_BF16) {
+    g_msg[0] = 0;
+    return fail(CTR_ERR_INVALID_ARGUMENT, "grad_dtype %d is not CTR_F32 or CTR_BF16", grad_dtype);
+  }
+  if (rounding != CTR_ROUND_NEAREST && rounding != CTR_ROUND_STOCHASTIC) {
+    g_msg[0] = 0;
+    return fail(CTR_ERR_INVALID_ARGUMENT, "unknown rounding %d", rounding);
+  }
+  return embbag_bwd_sgd_common(grad, grad_dtype == CTR_BF16, grad_stride_b, grad_stride_t,
+                               offsets, batch, num_tables, nnz, sorted_src, num_unique, table,
+                               dtype, total_rows, dim, uniq, lr, row_grads, nullptr, nullptr,
+                               rounding == CTR_ROUND_STOCHASTIC, seed, stream,
+                               "ctr_embbag_bwd_sgd_noalloc", nullptr, nullptr, true);
+}
+
+size_t ctr_embbag_bwd_noalloc_scratch_bytes(int64_t nnz, int32_t dim) {
+  if (nnz < 0 || dim <= 0 || dim % 4) return (size_t)-1;
+  return ctr::embbag_bwd_noalloc_bytes(nnz, dim);
+}
+
+size_t ctr_noalloc_scratch_capacity(void) { return ctr::kNoallocScratchBytes; }
 
 int32_t ctr_embbag_bwd_sgd(const float* grad, int64_t grad_stride_b, int64_t grad_stride_t,
                            const int64_t* offsets, int64_t batch, int32_t num_tables,

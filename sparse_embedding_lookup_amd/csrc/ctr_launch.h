@@ -48,6 +48,17 @@ hipError_t launch_embbag_bwd(const void* grad, bool grad_bf16, int64_t sb, int64
                              int sgd_mode, int64_t total_rows, const int64_t* uniq, float lr,
                              uint64_t seed, void* workspace, hipStream_t s,
                              void* l0_begin = nullptr, void* l0_end = nullptr);
+// The backward that allocates nothing: its carries and ticket live in a device array of
+// kNoallocScratchBytes per GPU (segreduce.hip); sorted_src is required, and the caller checks
+// embbag_bwd_noalloc_bytes(nnz, dim) <= kNoallocScratchBytes first.
+constexpr size_t kNoallocScratchBytes = size_t(64) << 20;
+size_t embbag_bwd_noalloc_bytes(int64_t nnz, int dim);
+hipError_t launch_embbag_bwd_noalloc(const void* grad, bool grad_bf16, int64_t sb, int64_t st,
+                                     const int64_t* offsets, int64_t batch, int32_t num_tables,
+                                     int dim, int64_t nnz, const int4* sorted_src,
+                                     float* row_grads, void* table, int sgd_mode,
+                                     int64_t total_rows, const int64_t* uniq, float lr,
+                                     uint64_t seed, hipStream_t s);
 // The fused backward + SGD entry (ctr_embbag_bwd_sgd_ex) with timing marks around its first
 // reduce-by-key kernel (capi.cpp).
 int32_t embbag_bwd_sgd_marked(const void* grad, int32_t grad_dtype, int64_t grad_stride_b,

@@ -15,6 +15,7 @@
 // out as at most two carries per chunk.  The carries (key, row) form a sequence of the same
 // kind, reduced by the same kernel, until one chunk is left: a tree of fixed shape whose
 // depth is ceil(log_chunk(n)).  No atomics anywhere.
+#include <mutex>
 #include <type_traits>
 
 #include "ctr_internal.h"
@@ -668,9 +669,63 @@ BwdWs carve(void* base, int64_t n, int dim) {
   return w;
 }
 
+// The carries and the ticket alone (the grouping comes from the unique's sorted_src).
+BwdWs carve_carries(void* base, int64_t n, int dim) {
+  BwdWs w{};
+  size_t off = 0;
+  char* b = static_cast<char*>(base);
+  auto take = [&](size_t sz) {
+    char* p = b ? b + off : nullptr;
+    off += align256(sz);
+    return p;
+  };
+  const int64_t chunk = chunk_positions(dim, kMinSlotDepth);
+  const int64_t c1 = 2 * ((n + chunk - 1) / chunk);
+  w.ticket = reinterpret_cast<uint32_t*>(take(256));
+  for (int k = 0; k < 2; ++k) {
+    w.ckeys[k] = reinterpret_cast<int32_t*>(take(sizeof(int32_t) * (size_t)(c1 + 2)));
+    w.crows[k] = reinterpret_cast<float*>(take(sizeof(float) * (size_t)(c1 + 2) * dim));
+  }
+  w.bytes = off;
+  return w;
+}
+
+}  // namespace
+
+// Scratch of the backward that allocates nothing (launch_embbag_bwd_noalloc): the carries
+// of the reduce-by-key levels and the finisher's ticket, for callers that cannot allocate.
+// Each GPU the library runs on holds its own copy until the process ends; every call on a
+// GPU shares it, so calls that overlap on one GPU race.
+static __device__ __align__(256) unsigned char scratch[kNoallocScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The device address of this GPU's scratch, taken once per device with that device current.
+// (The name `scratch` in host code is a host-side stand-in, never a device address.)
+hipError_t scratch_on_current_device(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
 }  // namespace
 
 size_t embbag_bwd_workspace_bytes(int64_t nnz, int dim) { return carve(nullptr, nnz, dim).bytes; }
+size_t embbag_bwd_noalloc_bytes(int64_t nnz, int dim) {
+  return carve_carries(nullptr, nnz, dim).bytes;
+}
 
 
 #define CTR_SEG_DISPATCH(G_, VPL_, ...)                                     \
@@ -723,20 +778,16 @@ static hipError_t segreduce_levels(const L0S& s0, int64_t nnz, int dim, float* r
   return e;
 }
 
-hipError_t launch_embbag_bwd(const void* grad, bool grad_bf16, int64_t sb, int64_t st,
-                             const int64_t* offsets,
-                             int64_t batch, int32_t num_tables, int dim, int64_t nnz,
-                             const int32_t* perm, const int32_t* inverse, const int4* sorted_src,
-                             const int32_t* num_unique, float* row_grads, void* table,
-                             int sgd_mode, int64_t total_rows, const int64_t* uniq, float lr,
-                             uint64_t seed, void* workspace, hipStream_t s, void* l0_begin,
+namespace {
+// The gradient source of level 0 and the reduce-by-key levels, into the carved workspace w.
+hipError_t embbag_bwd_levels(const BwdWs& w, const void* grad, bool grad_bf16, int64_t sb,
+                             int64_t st, const int64_t* offsets, int64_t batch,
+                             int32_t num_tables, int dim, int64_t nnz, const int32_t* perm,
+                             const int32_t* inverse, const int4* sorted_src, float* row_grads,
+                             void* table, int sgd_mode, int64_t total_rows, const int64_t* uniq,
+                             float lr, uint64_t seed, hipStream_t s, void* l0_begin,
                              void* l0_end) {
-  (void)num_unique;
-  if (nnz == 0) {                          // nothing to reduce; the marks still bracket it
-    const hipError_t e = record_mark(l0_begin, s);
-    return e == hipSuccess ? record_mark(l0_end, s) : e;
-  }
-  BwdWs w = carve(workspace, nnz, dim);
+  BwdWs wm = w;
   const int64_t num_bags = (int64_t)num_tables * batch;
 
   const int4* src = sorted_src;
@@ -755,17 +806,53 @@ hipError_t launch_embbag_bwd(const void* grad, bool grad_bf16, int64_t sb, int64
   auto levels = [&](const auto& s0) {
     using S0 = std::decay_t<decltype(s0)>;
     if (sgd_mode == 1)
-      return segreduce_levels<1, S0>(s0, nnz, dim, row_grads, sgd, w, s, l0_begin, l0_end);
+      return segreduce_levels<1, S0>(s0, nnz, dim, row_grads, sgd, wm, s, l0_begin, l0_end);
     if (sgd_mode == 2)
-      return segreduce_levels<2, S0>(s0, nnz, dim, row_grads, sgd, w, s, l0_begin, l0_end);
+      return segreduce_levels<2, S0>(s0, nnz, dim, row_grads, sgd, wm, s, l0_begin, l0_end);
     if (sgd_mode == 3)
-      return segreduce_levels<3, S0>(s0, nnz, dim, row_grads, sgd, w, s, l0_begin, l0_end);
-    return segreduce_levels<0, S0>(s0, nnz, dim, row_grads, sgd, w, s, l0_begin, l0_end);
+      return segreduce_levels<3, S0>(s0, nnz, dim, row_grads, sgd, wm, s, l0_begin, l0_end);
+    return segreduce_levels<0, S0>(s0, nnz, dim, row_grads, sgd, wm, s, l0_begin, l0_end);
   };
   const hipError_t e = grad_bf16 ? levels(L0SourceB{src, grad, sb, st, batch, num_bags})
                                  : levels(L0Source{src, grad, sb, st, batch, num_bags});
   if (e != hipSuccess) return e;
   return hipGetLastError();
+}
+}  // namespace
+
+hipError_t launch_embbag_bwd(const void* grad, bool grad_bf16, int64_t sb, int64_t st,
+                             const int64_t* offsets,
+                             int64_t batch, int32_t num_tables, int dim, int64_t nnz,
+                             const int32_t* perm, const int32_t* inverse, const int4* sorted_src,
+                             const int32_t* num_unique, float* row_grads, void* table,
+                             int sgd_mode, int64_t total_rows, const int64_t* uniq, float lr,
+                             uint64_t seed, void* workspace, hipStream_t s, void* l0_begin,
+                             void* l0_end) {
+  (void)num_unique;
+  if (nnz == 0) {                          // nothing to reduce; the marks still bracket it
+    const hipError_t e = record_mark(l0_begin, s);
+    return e == hipSuccess ? record_mark(l0_end, s) : e;
+  }
+  BwdWs w = carve(workspace, nnz, dim);
+  return embbag_bwd_levels(w, grad, grad_bf16, sb, st, offsets, batch, num_tables, dim, nnz, perm,
+                           inverse, sorted_src, row_grads, table, sgd_mode, total_rows, uniq, lr,
+                           seed, s, l0_begin, l0_end);
+}
+
+hipError_t launch_embbag_bwd_noalloc(const void* grad, bool grad_bf16, int64_t sb, int64_t st,
+                                     const int64_t* offsets, int64_t batch, int32_t num_tables,
+                                     int dim, int64_t nnz, const int4* sorted_src,
+                                     float* row_grads, void* table, int sgd_mode,
+                                     int64_t total_rows, const int64_t* uniq, float lr,
+                                     uint64_t seed, hipStream_t s) {
+  if (nnz == 0) return hipSuccess;
+  void* base = nullptr;
+  const hipError_t e = scratch_on_current_device(&base);
+  if (e != hipSuccess) return e;
+  BwdWs w = carve_carries(base, nnz, dim);   // fits: the caller checked the size
+  return embbag_bwd_levels(w, grad, grad_bf16, sb, st, offsets, batch, num_tables, dim, nnz,
+                           nullptr, nullptr, sorted_src, row_grads, table, sgd_mode, total_rows,
+                           uniq, lr, seed, s, nullptr, nullptr);
 }
 
 }  // namespace ctr

@@ -29,6 +29,8 @@ EXPORTED = [
     "ctr_fm_interaction_bwd", "ctr_dict_build", "ctr_dict_lookup", "ctr_dict_embbag_fwd",
     "ctr_dot_interaction_bwd_ex", "ctr_embbag_bwd_sgd_ex", "ctr_step_run_deep",
     "ctr_dense_fwd", "ctr_dense_bwd_sgd", "ctr_logistic_ne", "ctr_embbag_interaction_fwd",
+    "ctr_embbag_bwd_sgd_noalloc", "ctr_embbag_bwd_noalloc_scratch_bytes",
+    "ctr_noalloc_scratch_capacity",
 ]
 
 CTR_STEP_POOLED_INTERACTION, CTR_STEP_BATCH_MATRIX = 0, 1
@@ -103,6 +105,10 @@ def load() -> ctypes.CDLL:
         "ctr_dot_interaction_bwd_ex": (i32, [P, P, i64, i64, i32, i32, i32, i32, i32, P, P]),
         "ctr_embbag_bwd_sgd_ex": (i32, [P, i32, i64, i64, P, i64, i32, i64, P, P, P, i32, i64,
                                         i32, P, f32, i32, u64, P, P, PS, P]),
+        "ctr_embbag_bwd_sgd_noalloc": (i32, [P, i32, i64, i64, P, i64, i32, i64, P, P, P, i32,
+                                             i64, i32, P, f32, i32, u64, P, P]),
+        "ctr_embbag_bwd_noalloc_scratch_bytes": (sz, [i64, i32]),
+        "ctr_noalloc_scratch_capacity": (sz, []),
         "ctr_dict_build": (i32, [P, P, P, i64, P, i64, P, P]),
         "ctr_dict_lookup": (i32, [P, i64, P, i64, P, P]),
         "ctr_dict_embbag_fwd": (i32, [P, i64, P, i64, i32, P, i64, P, i64, i32, i32, P, i64,
@@ -351,6 +357,32 @@ def _bwd_ex(grad, sb, st, offsets, batch, num_tables, nnz, sorted_src, num_uniqu
             ctypes.c_float(lr), rounding, ctypes.c_uint64(seed & 0xFFFFFFFFFFFFFFFF),
             _ptr(row_grads), _ptr(workspace), ctypes.byref(wsb))
     return _run("ctr_embbag_bwd_sgd_ex", args, stream, prepare, row_grads)
+
+
+def ctr_embbag_bwd_sgd_noalloc(grad: torch.Tensor, grad_stride_b: int, grad_stride_t: int,
+                               offsets: torch.Tensor, batch: int, num_tables: int, nnz: int,
+                               sorted_src: torch.Tensor, num_unique: torch.Tensor,
+                               table: Optional[torch.Tensor], uniq: Optional[torch.Tensor],
+                               lr: float, row_grads: Optional[torch.Tensor] = None,
+                               rounding: int = CTR_ROUND_NEAREST, seed: int = 0, dim: int = 0,
+                               stream=None, prepare: bool = False):
+    """ctr_embbag_bwd_sgd_ex without a workspace: the library's per-GPU scratch holds the
+    reduce-by-key carries (table None: row sums into row_grads only; dim then required)."""
+    total_rows, d = (0, dim) if table is None else table.shape
+    args = (_ptr(grad), _dtype_code(grad), grad_stride_b, grad_stride_t, _ptr(offsets), batch,
+            num_tables, nnz, _ptr(sorted_src), _ptr(num_unique), _ptr(table),
+            CTR_F32 if table is None else _dtype_code(table), total_rows, d, _ptr(uniq),
+            ctypes.c_float(lr), rounding, ctypes.c_uint64(seed & 0xFFFFFFFFFFFFFFFF),
+            _ptr(row_grads))
+    return _run("ctr_embbag_bwd_sgd_noalloc", args, stream, prepare, row_grads)
+
+
+def noalloc_scratch_bytes(nnz: int, dim: int) -> int:
+    return int(load().ctr_embbag_bwd_noalloc_scratch_bytes(nnz, dim))
+
+
+def noalloc_scratch_capacity() -> int:
+    return int(load().ctr_noalloc_scratch_capacity())
 
 
 def ctr_sparse_sgd_sr(table: torch.Tensor, uniq: torch.Tensor, num_unique: torch.Tensor,

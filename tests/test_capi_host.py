@@ -369,3 +369,24 @@ def test_dense_and_head_bad_args():
         ctr.CTR_ERR_INVALID_ARGUMENT
     assert lib.ctr_logistic_ne(FAKE, 1, FAKE, 5, None, None, 1, None, None) == \
         ctr.CTR_ERR_INVALID_ARGUMENT
+
+
+def test_noalloc_backward_limits_and_rejections():
+    """The backward that allocates nothing: a fixed per-GPU scratch (64 MiB), a size query,
+    and batches beyond it rejected on the host before any launch (fake device pointers)."""
+    lib = _lib()
+    assert lib.ctr_noalloc_scratch_capacity() == 64 << 20
+    small = lib.ctr_embbag_bwd_noalloc_scratch_bytes(327680, 64)
+    assert 0 < small < 64 << 20
+    assert lib.ctr_embbag_bwd_noalloc_scratch_bytes(67_000_000, 128) > 64 << 20
+    assert lib.ctr_embbag_bwd_noalloc_scratch_bytes(-1, 64) == ctypes.c_size_t(-1).value
+    args = (FAKE, 1, 65 * 128, 128, FAKE, 32768, 64, 67_000_000, FAKE, FAKE, FAKE, 1,
+            256_000_000, 128, FAKE, ctypes.c_float(0.01), 0, ctypes.c_uint64(0), None, None)
+    assert lib.ctr_embbag_bwd_sgd_noalloc(*args) == 2          # CTR_ERR_UNSUPPORTED
+    assert b"scratch" in lib.ctr_last_error()
+    bad = list(args)
+    bad[1] = 7                                                 # unknown gradient dtype
+    assert lib.ctr_embbag_bwd_sgd_noalloc(*bad) == 1
+    bad = list(args)
+    bad[16] = 9                                                # unknown rounding
+    assert lib.ctr_embbag_bwd_sgd_noalloc(*bad) == 1
