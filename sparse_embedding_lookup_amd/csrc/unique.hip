@@ -15,9 +15,12 @@
 //   downsweep each block ranks its tiles stably with wave64 ballot "multisplit" (one
 //             ballot per digit bit gives the mask of lanes holding the same digit), stages
 //             the tile in LDS in digit order and writes it out in runs per digit.
-// The payload is the occurrence index and, when bags are given, the occurrence's bag, so
-// that the finalize can emit (distinct-row index, bag) per sorted position for the
-// backward's reduce-by-key.  No inter-block waiting anywhere.
+// The payload is the occurrence index alone.  When bags are given, key formation also writes
+// each occurrence's bag in occurrence order, and the finalize reads it through the sorted
+// occurrence index to emit (distinct-row index, bag) per sorted position for the backward's
+// reduce-by-key: the sorted positions of one table read one table's stretch of that array, a
+// few MB that the caches hold, instead of a third array moved through every pass.  No
+// inter-block waiting anywhere.
 #include <utility>
 
 #include "ctr_internal.h"
@@ -85,11 +88,14 @@ __device__ __forceinline__ int64_t floor_mod(int64_t id, int64_t m) {
 // Bags known: `parts` waves share one group of 64 consecutive bags; lane l holds the end of
 // bag s0 + l and every occurrence finds its bag by a 6-step binary search over those ends
 // (shuffles); each wave takes every parts-th stretch of 64 occurrences of the group.
-template <bool ID64, typename K>
+// B16: the bag is stored as its sample index (bag - table * batch, batch <= 65536) in 16 bits,
+// which halves the array the finalize reads through the occurrence index; the table comes
+// back from the key.
+template <bool ID64, typename K, bool B16>
 __global__ __launch_bounds__(kThreads) void form_keys_bags_kernel(
     const void* __restrict__ ids, int64_t n, const int64_t* __restrict__ offsets, int64_t batch,
     int64_t num_bags, const int64_t* __restrict__ row_base, int64_t modulus, uint64_t flip,
-    int parts, K* __restrict__ keys, uint32_t* __restrict__ bags) {
+    int parts, K* __restrict__ keys, void* __restrict__ bags) {
   const int lane = threadIdx.x & 63;
   const int64_t wave = ((int64_t)blockIdx.x * kThreads + threadIdx.x) >> 6;
   const int64_t s0 = (wave / parts) * 64;
@@ -115,7 +121,10 @@ __global__ __launch_bounds__(kThreads) void form_keys_bags_kernel(
       int64_t key = floor_mod(id, modulus);
       if (row_base) key += row_base[bag / batch];
       keys[i] = (K)((uint64_t)key ^ flip);
-      bags[i] = (uint32_t)bag;
+      if constexpr (B16)
+        static_cast<uint16_t*>(bags)[i] = (uint16_t)(bag - (bag / batch) * batch);
+      else
+        static_cast<uint32_t*>(bags)[i] = (uint32_t)bag;
     }
   }
 }
@@ -212,7 +221,6 @@ template <typename K, int ITEMS>
 struct DownsweepSmem {
   K keys[kThreads * ITEMS];
   uint32_t vals[kThreads * ITEMS];
-  uint32_t bags[kThreads * ITEMS];
   uint32_t wcnt[4][kBuckets];
   uint32_t run[kBuckets];
   uint32_t tstart[kBuckets];
@@ -220,14 +228,12 @@ struct DownsweepSmem {
   uint32_t tmp[4];
 };
 
-// IDENT: payload of pass 0 is the element index.  BAGS: a second payload (the bag) rides
-// along.  FUSED: few blocks, so this block sums the digit counts of the blocks before it
-// itself instead of reading a separate scan's output.
-template <typename K, int ITEMS, bool IDENT, bool BAGS, bool FUSED>
+// IDENT: payload of pass 0 is the element index.  FUSED: few blocks, so this block sums the
+// digit counts of the blocks before it itself instead of reading a separate scan's output.
+template <typename K, int ITEMS, bool IDENT, bool FUSED>
 __global__ __launch_bounds__(kThreads) void radix_downsweep_kernel(
     const K* __restrict__ keys_in, const uint32_t* __restrict__ vals_in,
-    const uint32_t* __restrict__ bags_in, K* __restrict__ keys_out,
-    uint32_t* __restrict__ vals_out, uint32_t* __restrict__ bags_out, int64_t n, int shift,
+    K* __restrict__ keys_out, uint32_t* __restrict__ vals_out, int64_t n, int shift,
     int nbits, int64_t per_block, const uint32_t* __restrict__ hist,
     const uint32_t* __restrict__ totals, int nblocks, int ld) {
   constexpr int kT = kThreads * ITEMS;
@@ -275,7 +281,6 @@ __global__ __launch_bounds__(kThreads) void radix_downsweep_kernel(
   for (int64_t tile = beg; tile < end; tile += kT) {
     K key[ITEMS];
     uint32_t val[ITEMS];
-    uint32_t bag[ITEMS];
     uint32_t rank[ITEMS];
     bool valid[ITEMS];
 #pragma unroll
@@ -284,22 +289,28 @@ __global__ __launch_bounds__(kThreads) void radix_downsweep_kernel(
       valid[k] = e < end;
       key[k] = valid[k] ? keys_in[e] : (K)0;
       val[k] = valid[k] ? (IDENT ? (uint32_t)e : vals_in[e]) : 0u;
-      bag[k] = (BAGS && valid[k]) ? bags_in[e] : 0u;
     }
     for (int d = lane; d < kBuckets; d += 64) sm.wcnt[wave][d] = 0;
     __builtin_amdgcn_wave_barrier();
+    // Rank within the wave: the lanes of an item that share a digit (ballot multisplit) add
+    // their count to the wave's bin with one returning LDS atomic from their lowest lane.  A
+    // wave's LDS operations complete in issue order, so item k's atomics see items 0..k-1,
+    // and every item's atomic is in flight before any result is used.
+    uint64_t mm[ITEMS];
+    uint32_t pre[ITEMS];
 #pragma unroll
     for (int k = 0; k < ITEMS; ++k) {
       const uint32_t d = (uint32_t)(key[k] >> shift) & mask;
       const uint64_t active = __ballot(valid[k]);
-      const uint64_t m = match_digit(d, nbits, active);
-      const uint32_t r = (uint32_t)__popcll(m & lt);
-      uint32_t pre = 0;
-      if (valid[k]) pre = sm.wcnt[wave][d];
-      __builtin_amdgcn_wave_barrier();
-      if (valid[k] && r == 0) sm.wcnt[wave][d] = pre + (uint32_t)__popcll(m);
-      __builtin_amdgcn_wave_barrier();
-      rank[k] = pre + r;
+      mm[k] = match_digit(d, nbits, active);
+      pre[k] = 0u;
+      if (valid[k] && (mm[k] & lt) == 0ull)
+        pre[k] = atomicAdd(&sm.wcnt[wave][d], (uint32_t)__popcll(mm[k]));
+    }
+#pragma unroll
+    for (int k = 0; k < ITEMS; ++k) {
+      const int leader = mm[k] ? (int)__builtin_ctzll(mm[k]) : 0;   // lowest lane of the digit
+      rank[k] = (uint32_t)__shfl((int)pre[k], leader, 64) + (uint32_t)__popcll(mm[k] & lt);
     }
     __syncthreads();
     {
@@ -323,7 +334,6 @@ __global__ __launch_bounds__(kThreads) void radix_downsweep_kernel(
         const uint32_t pos = sm.tstart[d] + sm.wcnt[wave][d] + rank[k];
         sm.keys[pos] = key[k];
         sm.vals[pos] = val[k];
-        if (BAGS) sm.bags[pos] = bag[k];
       }
     }
     __syncthreads();
@@ -334,7 +344,6 @@ __global__ __launch_bounds__(kThreads) void radix_downsweep_kernel(
       const uint32_t o = sm.run[d] + (uint32_t)q - sm.tstart[d];
       keys_out[o] = kk;
       vals_out[o] = sm.vals[q];
-      if (BAGS) bags_out[o] = sm.bags[q];
     }
     __syncthreads();
     sm.run[threadIdx.x] += sm.tcount[threadIdx.x];
@@ -413,22 +422,31 @@ __global__ __launch_bounds__(1024) void heads_scan_kernel(uint32_t* __restrict__
 }
 
 // sorted_src[p] = (distinct-row index of position p, bag of its occurrence, key as two
-// words); without bags the occurrence is its own bag.  Every load of the tile is issued
-// first (keys, the key before each position, occurrence, bag; and, when FUSED, the head
-// counts of the earlier tiles), then one barrier publishes the per-round wave head counts.
+// words); bag_of (occurrence order) gives the bag, and without bags the occurrence is its
+// own bag.  Every load of the tile is issued first (keys, the key before each position,
+// occurrence, then the bags through the occurrences; and, when FUSED, the head counts of the
+// earlier tiles), then one barrier publishes the per-round wave head counts.
 // FUSED: few tiles, so the block sums the head counts of the tiles before it itself, and
 // the last block publishes U.
-template <typename K, bool FUSED>
+// B16: bag_of holds 16-bit sample indices (form_keys_bags_kernel<.., true>); the bag is
+// table * batch + sample with the table the last one whose row_base is <= the key.
+constexpr int kFinMaxTables = 1024;
+template <typename K, bool FUSED, bool B16>
 __global__ __launch_bounds__(kThreads) void unique_finalize_kernel(
-    const K* __restrict__ sk, const uint32_t* __restrict__ sv, const uint32_t* __restrict__ sbag,
+    const K* __restrict__ sk, const uint32_t* __restrict__ sv, const void* __restrict__ bag_of,
     int64_t n, uint64_t flip, const uint32_t* __restrict__ tile_heads, int64_t ntiles,
     int64_t* __restrict__ uniq, int32_t* __restrict__ inverse, int32_t* __restrict__ seg_offsets,
-    int4* __restrict__ sorted_src, int32_t* __restrict__ num_unique) {
+    int4* __restrict__ sorted_src, int32_t* __restrict__ num_unique,
+    const int64_t* __restrict__ row_base, int num_tables, int64_t batch) {
   __shared__ uint32_t wcnt[kFinRounds][4];
   __shared__ uint32_t wtile[2][4];
+  __shared__ int64_t s_rb[B16 ? kFinMaxTables : 1];
+  if constexpr (B16)
+    for (int t = threadIdx.x; t < num_tables; t += kThreads) s_rb[t] = row_base[t];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const uint64_t le = (lane == 63) ? ~0ull : ((2ull << lane) - 1ull);
-  const int64_t t0 = (int64_t)blockIdx.x * kFinTile;
+  const int64_t tile = blockIdx.x;
+  const int64_t t0 = tile * kFinTile;
 
   K key[kFinRounds];
   K prev[kFinRounds];
@@ -441,14 +459,22 @@ __global__ __launch_bounds__(kThreads) void unique_finalize_kernel(
     key[j] = ok ? sk[p] : (K)0;
     prev[j] = (ok && p > 0) ? sk[p - 1] : (K)0;
     occ[j] = ok ? sv[p] : 0u;
-    bag[j] = (ok && sbag) ? sbag[p] : occ[j];
+  }
+#pragma unroll
+  for (int j = 0; j < kFinRounds; ++j) {
+    const int64_t p = t0 + (int64_t)j * kThreads + threadIdx.x;
+    const bool ok = p < n && bag_of && occ[j] < (uint64_t)n;
+    if constexpr (B16)
+      bag[j] = ok ? (uint32_t) static_cast<const uint16_t*>(bag_of)[occ[j]] : occ[j];
+    else
+      bag[j] = ok ? static_cast<const uint32_t*>(bag_of)[occ[j]] : occ[j];
   }
   uint32_t before_tile = 0, all_tiles = 0;
   if (FUSED) {
     for (int64_t t = threadIdx.x; t < ntiles; t += kThreads) {
       const uint32_t c = tile_heads[t];
       all_tiles += c;
-      if (t < (int64_t)blockIdx.x) before_tile += c;
+      if (t < tile) before_tile += c;
     }
     for (int o = 32; o > 0; o >>= 1) {
       before_tile += __shfl_xor(before_tile, o, 64);
@@ -471,13 +497,13 @@ __global__ __launch_bounds__(kThreads) void unique_finalize_kernel(
   uint32_t base;
   if (FUSED) {
     base = wtile[0][0] + wtile[0][1] + wtile[0][2] + wtile[0][3];
-    if (blockIdx.x == gridDim.x - 1 && threadIdx.x == 0) {
+    if (tile == ntiles - 1 && threadIdx.x == 0) {
       const uint32_t tot = wtile[1][0] + wtile[1][1] + wtile[1][2] + wtile[1][3];
       *num_unique = (int32_t)tot;
       if (seg_offsets) seg_offsets[tot] = (int32_t)n;
     }
   } else {
-    base = tile_heads[blockIdx.x];
+    base = tile_heads[tile];
   }
 #pragma unroll
   for (int j = 0; j < kFinRounds; ++j) {
@@ -493,8 +519,18 @@ __global__ __launch_bounds__(kThreads) void unique_finalize_kernel(
         if (seg_offsets) seg_offsets[r] = (int32_t)p;
       }
       if (occ[j] < (uint64_t)n) inverse[occ[j]] = (int32_t)r;
-      if (sorted_src)
-        sorted_src[p] = make_int4((int32_t)r, (int32_t)bag[j], (int32_t)kk, (int32_t)(kk >> 32));
+      if (sorted_src) {
+        uint32_t bg = bag[j];
+        if constexpr (B16) {
+          int lo = 0, hi = num_tables - 1;       // last table whose first row is <= the key
+          while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if ((uint64_t)s_rb[mid] <= kk) lo = mid; else hi = mid - 1;
+          }
+          bg += (uint32_t)((int64_t)lo * batch);
+        }
+        sorted_src[p] = make_int4((int32_t)r, (int32_t)bg, (int32_t)kk, (int32_t)(kk >> 32));
+      }
     }
   }
 }
@@ -513,8 +549,7 @@ struct UniqueWs {
   void* keys_b;
   uint32_t* vals_a;
   uint32_t* vals_b;
-  uint32_t* bags_a;
-  uint32_t* bags_b;
+  uint32_t* bags_a;           // bag of each occurrence, occurrence order
   uint32_t* hist;
   uint32_t* totals;
   uint32_t* tile_heads;
@@ -535,7 +570,6 @@ UniqueWs carve(void* base, int64_t n) {
   w.vals_a = reinterpret_cast<uint32_t*>(take(sizeof(uint32_t) * (size_t)n));
   w.vals_b = reinterpret_cast<uint32_t*>(take(sizeof(uint32_t) * (size_t)n));
   w.bags_a = reinterpret_cast<uint32_t*>(take(sizeof(uint32_t) * (size_t)n));
-  w.bags_b = reinterpret_cast<uint32_t*>(take(sizeof(uint32_t) * (size_t)n));
   w.hist = reinterpret_cast<uint32_t*>(take(sizeof(uint32_t) * kBuckets * kMaxBlocks));
   w.totals = reinterpret_cast<uint32_t*>(take(sizeof(uint32_t) * kBuckets));
   w.tile_heads = reinterpret_cast<uint32_t*>(
@@ -545,33 +579,29 @@ UniqueWs carve(void* base, int64_t n) {
 }
 
 template <typename K, int ITEMS>
-void radix_pass(bool first, bool bags, const K* kin, const uint32_t* vin, const uint32_t* bin,
-                K* kout, uint32_t* vout, uint32_t* bout, int64_t n, int shift, int nbits,
-                int64_t per_block, uint32_t* hist, uint32_t* totals, int nblocks,
-                hipStream_t s) {
+void radix_pass(bool first, const K* kin, const uint32_t* vin, K* kout, uint32_t* vout,
+                int64_t n, int shift, int nbits, int64_t per_block, uint32_t* hist,
+                uint32_t* totals, int nblocks, hipStream_t s) {
   const int ld = (nblocks + 3) & ~3;
   radix_upsweep_kernel<K><<<nblocks, kThreads, 0, s>>>(kin, n, shift, nbits, per_block, hist,
                                                        ld);
   const bool fused = nblocks <= kFusedScanBlocks;
   if (!fused) radix_scan_kernel<<<kBuckets, kThreads, 0, s>>>(hist, nblocks, ld, totals);
-#define CTR_DS(I, B, FU)                                                                   \
-  radix_downsweep_kernel<K, ITEMS, I, B, FU><<<nblocks, kThreads, 0, s>>>(                 \
-      kin, vin, bin, kout, vout, bout, n, shift, nbits, per_block, hist, totals, nblocks, ld)
-#define CTR_DS2(I, B) \
-  if (fused) CTR_DS(I, B, true); else CTR_DS(I, B, false)
+#define CTR_DS(I, FU)                                                                      \
+  radix_downsweep_kernel<K, ITEMS, I, FU><<<nblocks, kThreads, 0, s>>>(                    \
+      kin, vin, kout, vout, n, shift, nbits, per_block, hist, totals, nblocks, ld)
   if (first) {
-    if (bags) { CTR_DS2(true, true); } else { CTR_DS2(true, false); }
+    if (fused) CTR_DS(true, true); else CTR_DS(true, false);
   } else {
-    if (bags) { CTR_DS2(false, true); } else { CTR_DS2(false, false); }
+    if (fused) CTR_DS(false, true); else CTR_DS(false, false);
   }
-#undef CTR_DS2
 #undef CTR_DS
 }
 
 template <typename K, int ITEMS>
-void radix_sort(int key_bits, bool bags, K* keys_a, K* keys_b, uint32_t* vbuf0, uint32_t* vbuf1,
-                uint32_t* bags_a, uint32_t* bags_b, int64_t n, uint32_t* hist, uint32_t* totals,
-                const K** sk, const uint32_t** sv, const uint32_t** sb, hipStream_t s) {
+void radix_sort(int key_bits, K* keys_a, K* keys_b, uint32_t* vbuf0, uint32_t* vbuf1, int64_t n,
+                uint32_t* hist, uint32_t* totals, const K** sk, const uint32_t** sv,
+                hipStream_t s) {
   constexpr int kT = kThreads * ITEMS;
   const int64_t ntiles = (n + kT - 1) / kT;
   int nblocks = (int)(ntiles < kMaxBlocks ? ntiles : kMaxBlocks);
@@ -583,23 +613,19 @@ void radix_sort(int key_bits, bool bags, K* keys_a, K* keys_b, uint32_t* vbuf0, 
   K* kout = keys_b;
   uint32_t* vb[2] = {vbuf0, vbuf1};
   const uint32_t* vin = nullptr;
-  uint32_t* bin = bags_a;
-  uint32_t* bout = bags_b;
   int shift = 0;
   for (int p = 0; p < passes; ++p) {
     const int left = key_bits - shift;
     const int nbits = (left + (passes - p) - 1) / (passes - p);   // spread bits evenly
     uint32_t* vout = vb[(passes - 1 - p) & 1];                       // last pass -> vbuf0
-    radix_pass<K, ITEMS>(p == 0, bags, kin, vin, bin, kout, vout, bout, n, shift, nbits,
-                         per_block, hist, totals, nblocks, s);
+    radix_pass<K, ITEMS>(p == 0, kin, vin, kout, vout, n, shift, nbits, per_block, hist, totals,
+                         nblocks, s);
     shift += nbits;
     vin = vout;
     std::swap(kin, kout);
-    std::swap(bin, bout);
   }
   *sk = kin;
   *sv = vin;
-  *sb = bags ? bin : nullptr;
 }
 
 template <typename K>
@@ -609,6 +635,9 @@ hipError_t unique_impl(const void* ids, bool ids64, int64_t n, const int64_t* of
                        int32_t* inverse, int32_t* num_unique, int32_t* perm,
                        int32_t* seg_offsets, int4* sorted_src, UniqueWs& w, hipStream_t s) {
   const bool bags = offsets != nullptr && sorted_src != nullptr;
+  // 16-bit sample indices for the bags when the table can be told from the key
+  const bool b16 = bags && row_base != nullptr && batch <= 65536 &&
+                   num_tables <= kFinMaxTables && sizeof(K) == 4 && flip == 0;
   K* keys_a = static_cast<K*>(w.keys_a);
   K* keys_b = static_cast<K*>(w.keys_b);
 
@@ -623,14 +652,15 @@ hipError_t unique_impl(const void* ids, bool ids64, int64_t n, const int64_t* of
     if (parts < 1) parts = 1;
     const int64_t blocks = (groups * parts + 3) / 4;
     if (blocks > 0) {
-      if (ids64)
-        form_keys_bags_kernel<true, K><<<(unsigned)blocks, kThreads, 0, s>>>(
-            ids, n, offsets, batch, num_bags, row_base, modulus, flip, (int)parts, keys_a,
-            w.bags_a);
-      else
-        form_keys_bags_kernel<false, K><<<(unsigned)blocks, kThreads, 0, s>>>(
-            ids, n, offsets, batch, num_bags, row_base, modulus, flip, (int)parts, keys_a,
-            w.bags_a);
+#define CTR_FK(I64, B)                                                                     \
+  form_keys_bags_kernel<I64, K, B><<<(unsigned)blocks, kThreads, 0, s>>>(                  \
+      ids, n, offsets, batch, num_bags, row_base, modulus, flip, (int)parts, keys_a, w.bags_a)
+      if (ids64) {
+        if (b16) CTR_FK(true, true); else CTR_FK(true, false);
+      } else {
+        if (b16) CTR_FK(false, true); else CTR_FK(false, false);
+      }
+#undef CTR_FK
     }
   } else {
     int64_t blocks = (n + kThreads - 1) / kThreads;
@@ -643,33 +673,33 @@ hipError_t unique_impl(const void* ids, bool ids64, int64_t n, const int64_t* of
                                                                             flip, keys_a);
   }
 
-  // a2: stable LSD radix sort of (key, occurrence[, bag]) over the live key bits; values
-  // ping-pong so that the last pass lands in `perm` when the caller wants it.
+  // a2: stable LSD radix sort of (key, occurrence) over the live key bits; values ping-pong
+  // so that the last pass lands in `perm` when the caller wants it.  The bags stay in
+  // occurrence order (w.bags_a) for the finalize.
   uint32_t* vbuf0 = perm ? reinterpret_cast<uint32_t*>(perm) : w.vals_a;
   uint32_t* vbuf1 = perm ? w.vals_a : w.vals_b;
   const K* sk;
   const uint32_t* sv;
-  const uint32_t* sb;
   if (n <= (1 << 20))   // small batches: shorter tiles, more blocks, shorter chains
-    radix_sort<K, 4>(key_bits, bags, keys_a, keys_b, vbuf0, vbuf1, w.bags_a, w.bags_b, n,
-                     w.hist, w.totals, &sk, &sv, &sb, s);
+    radix_sort<K, 4>(key_bits, keys_a, keys_b, vbuf0, vbuf1, n, w.hist, w.totals, &sk, &sv, s);
   else
-    radix_sort<K, 8>(key_bits, bags, keys_a, keys_b, vbuf0, vbuf1, w.bags_a, w.bags_b, n,
-                     w.hist, w.totals, &sk, &sv, &sb, s);
+    radix_sort<K, 8>(key_bits, keys_a, keys_b, vbuf0, vbuf1, n, w.hist, w.totals, &sk, &sv, s);
+  const void* sb = bags ? w.bags_a : nullptr;   // bag of each occurrence, occurrence order
 
   // finalize: heads, their scan, and the scatter of uniq / seg / inverse / sorted_src
   const int64_t ftiles = (n + kFinTile - 1) / kFinTile;
   heads_count_kernel<K><<<(unsigned)ftiles, kThreads, 0, s>>>(sk, n, w.tile_heads);
+#define CTR_FIN(FU, B)                                                                     \
+  unique_finalize_kernel<K, FU, B><<<(unsigned)ftiles, kThreads, 0, s>>>(                  \
+      sk, sv, sb, n, flip, w.tile_heads, ftiles, uniq, inverse, seg_offsets, sorted_src,   \
+      num_unique, row_base, num_tables, batch)
   if (ftiles <= kFusedHeadTiles) {
-    unique_finalize_kernel<K, true><<<(unsigned)ftiles, kThreads, 0, s>>>(
-        sk, sv, sb, n, flip, w.tile_heads, ftiles, uniq, inverse, seg_offsets, sorted_src,
-        num_unique);
+    if (b16) CTR_FIN(true, true); else CTR_FIN(true, false);
   } else {
     heads_scan_kernel<<<1, 1024, 0, s>>>(w.tile_heads, ftiles, n, num_unique, seg_offsets);
-    unique_finalize_kernel<K, false><<<(unsigned)ftiles, kThreads, 0, s>>>(
-        sk, sv, sb, n, flip, w.tile_heads, ftiles, uniq, inverse, seg_offsets, sorted_src,
-        num_unique);
+    if (b16) CTR_FIN(false, true); else CTR_FIN(false, false);
   }
+#undef CTR_FIN
   return hipGetLastError();
 }
 
