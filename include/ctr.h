@@ -98,11 +98,16 @@ const char* ctr_last_error(void);
  *                    reaches the gradient row and the table row of a position in one read.
  * Key range: with row_base the keys must lie in [0, total_rows); with only a modulus in
  * [0, key_modulus); otherwise any int64.  The sort covers only the live key bits.
+ * max_table_rows (0: unknown): the row count of the largest table.  With row_base and no
+ * modulus, the ids of table t must then lie in [0, min(rows_t, max_table_rows)), and the
+ * sort may run per table over the bits of max_table_rows - 1 only (each table's occurrences
+ * are one contiguous stretch, bags being table-major); the outputs are the same.
  * n == 0 is legal: U = 0, seg_offsets[0] = 0.
  */
 int32_t ctr_unique_ids(const void* ids, int32_t id_type, int64_t n,
                        const int64_t* offsets, int64_t batch, int32_t num_tables,
-                       const int64_t* row_base, int64_t total_rows, int64_t key_modulus,
+                       const int64_t* row_base, int64_t total_rows, int64_t max_table_rows,
+                       int64_t key_modulus,
                        int64_t* uniq, int32_t* inverse, int32_t* num_unique,
                        int32_t* perm, int32_t* seg_offsets, int32_t* sorted_src,
                        void* workspace, size_t* workspace_bytes, void* stream);
@@ -489,6 +494,8 @@ typedef struct {
   void* ws_unique2;               /* ctr_step_run_deep: the second side stream's unique */
   size_t ws_unique2_bytes;        /*   workspace (two uniques run at once) */
   int32_t mark_stage;             /* CTR_MARK_POOLING (0) or CTR_MARK_BACKWARD (1) */
+  int64_t max_table_rows;         /* pooled step: rows of the largest table, or 0 (see
+                                     ctr_unique_ids) */
 } ctr_step_t;
 
 /*

@@ -97,7 +97,8 @@ const char* ctr_last_error(void) { return g_msg; }
 
 int32_t ctr_unique_ids(const void* ids, int32_t id_type, int64_t n, const int64_t* offsets,
                        int64_t batch, int32_t num_tables, const int64_t* row_base,
-                       int64_t total_rows, int64_t key_modulus, int64_t* uniq,
+                       int64_t total_rows, int64_t max_table_rows, int64_t key_modulus,
+                       int64_t* uniq,
                        int32_t* inverse, int32_t* num_unique, int32_t* perm,
                        int32_t* seg_offsets, int32_t* sorted_src, void* workspace,
                        size_t* workspace_bytes, void* stream) {
@@ -115,6 +116,7 @@ int32_t ctr_unique_ids(const void* ids, int32_t id_type, int64_t n, const int64_
       return fail(CTR_ERR_INVALID_ARGUMENT, "bad batch %lld", (long long)batch);
     if (total_rows < 1) return fail(CTR_ERR_INVALID_ARGUMENT, "total_rows must be >= 1");
   }
+  if (max_table_rows < 0) return fail(CTR_ERR_INVALID_ARGUMENT, "max_table_rows < 0");
   const size_t need = ctr::unique_workspace_bytes(n);
   if (!workspace) {
     *workspace_bytes = need;
@@ -139,8 +141,18 @@ int32_t ctr_unique_ids(const void* ids, int32_t id_type, int64_t n, const int64_
     is_signed = true;
   }
   if (bits < 1) bits = 1;
+  // Tables as segments: sort the local row bits within each table when that takes fewer
+  // passes of at most 8 bits than the global key, and (t << L) | local fits 32 bits.
+  int seg_bits = 0;
+  if (row_base && max_table_rows > 0 && num_tables >= 2 && num_tables <= 512 &&
+      key_modulus == 0) {
+    const int L = max_table_rows > 1 ? bitlen((uint64_t)(max_table_rows - 1)) : 1;
+    if (L + bitlen((uint64_t)(num_tables - 1)) <= 32 && (L + 7) / 8 < (bits + 7) / 8)
+      seg_bits = L;
+  }
   return hip_status(ctr::launch_unique(ids, id_type == CTR_I64, n, offsets, batch, num_tables,
-                                       row_base, key_modulus, bits, is_signed, uniq, inverse,
+                                       row_base, key_modulus, bits, seg_bits, is_signed, uniq,
+                                       inverse,
                                        num_unique, perm, seg_offsets,
                                        reinterpret_cast<int4*>(sorted_src), workspace,
                                        (hipStream_t)stream),

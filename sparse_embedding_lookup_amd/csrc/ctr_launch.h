@@ -13,10 +13,12 @@ namespace ctr {
 
 // unique.hip
 size_t unique_workspace_bytes(int64_t n);
+// seg_bits > 0: the table-segmented sort over seg_bits local row bits (row_base and offsets
+// given, (num_tables - 1) << seg_bits below 2^32, at most 512 tables).
 hipError_t launch_unique(const void* ids, bool ids64, int64_t n, const int64_t* offsets,
                          int64_t batch, int32_t num_tables, const int64_t* row_base,
-                         int64_t modulus, int key_bits, bool key_signed, int64_t* uniq,
-                         int32_t* inverse, int32_t* num_unique, int32_t* perm,
+                         int64_t modulus, int key_bits, int seg_bits, bool key_signed,
+                         int64_t* uniq, int32_t* inverse, int32_t* num_unique, int32_t* perm,
                          int32_t* seg_offsets, int4* sorted_src, void* workspace,
                          hipStream_t s);
 

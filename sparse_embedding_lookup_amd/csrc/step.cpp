@@ -47,10 +47,11 @@ int32_t unique_into(const ctr_step_t* d, int set, void* stream, int ws = 0) {
   size_t wsb = ws ? d->ws_unique2_bytes : d->ws_unique_bytes;
   if (d->kind == CTR_STEP_POOLED_INTERACTION)
     return ctr_unique_ids(d->indices, d->index_type, d->nnz, d->offsets, d->batch,
-                          d->num_tables, d->row_base, d->total_rows, 0, d->uniq[set],
+                          d->num_tables, d->row_base, d->total_rows, d->max_table_rows, 0,
+                          d->uniq[set],
                           d->inverse[set], d->num_unique[set], d->perm[set], d->seg_offsets[set],
                           d->sorted_src[set], wsp, &wsb, stream);
-  return ctr_unique_ids(d->indices, d->index_type, d->nnz, nullptr, 0, 0, nullptr, 0,
+  return ctr_unique_ids(d->indices, d->index_type, d->nnz, nullptr, 0, 0, nullptr, 0, 0,
                         d->key_modulus, d->uniq[set], d->inverse[set], d->num_unique[set],
                         d->perm[set], d->seg_offsets[set], d->sorted_src[set], wsp, &wsb, stream);
 }

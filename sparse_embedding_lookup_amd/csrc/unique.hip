@@ -15,6 +15,13 @@
 //   downsweep each block ranks its tiles stably with wave64 ballot "multisplit" (one
 //             ballot per digit bit gives the mask of lanes holding the same digit), stages
 //             the tile in LDS in digit order and writes it out in runs per digit.
+// Tables as segments: when the caller gives the largest table's row count, the occurrences
+// of one table are contiguous (bags are table-major), and table t's keys are row_base[t]
+// plus a local row below 2^L, the sort key is (t << L) | local and every radix pass sorts
+// the L local bits within each table's range only (a pass's blocks each hold one table's
+// stretch; a block's digit offsets are its table's start plus the prefixes within that
+// table).  The table bits are never sorted: Large's 28-bit keys take three passes of local
+// rows instead of four, and the finalize rebuilds row_base[t] + local.
 // The payload is the occurrence index alone.  When bags are given, key formation also writes
 // each occurrence's bag in occurrence order, and the finalize reads it through the sorted
 // occurrence index to emit (distinct-row index, bag) per sorted position for the backward's
@@ -49,6 +56,54 @@ __device__ __forceinline__ uint64_t match_digit(uint32_t d, int nbits, uint64_t 
     m &= bit ? bal : ~bal;
   }
   return m;
+}
+
+// Radix block of the table-segmented sort: the table it belongs to (-1: no work), the
+// table's first block and the next table's first block, the table's first position, and the
+// block's range of positions.
+constexpr int kMaxSegTables = 512;
+struct SegBlock {
+  int32_t seg, first, next, pad;
+  int64_t seg_beg, beg, end;
+};
+
+// One block: each table's stretch of positions [offsets[t*batch], offsets[(t+1)*batch]) is
+// cut into ceil(len / per_block) blocks; block b learns its table, its range and the first
+// blocks of its table and the next.
+__global__ __launch_bounds__(1024) void seg_blocks_kernel(const int64_t* __restrict__ offsets,
+                                                          int64_t batch, int num_tables,
+                                                          int64_t n, int64_t per_block,
+                                                          int nblocks,
+                                                          SegBlock* __restrict__ blk) {
+  __shared__ int64_t start[kMaxSegTables + 1];
+  __shared__ int32_t first[kMaxSegTables + 1];
+  for (int t = threadIdx.x; t <= num_tables; t += blockDim.x)
+    start[t] = clamp64(offsets[(int64_t)t * batch], 0, n);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int32_t acc = 0;
+    for (int t = 0; t < num_tables; ++t) {
+      first[t] = acc;
+      const int64_t len = start[t + 1] > start[t] ? start[t + 1] - start[t] : 0;
+      acc += (int32_t)((len + per_block - 1) / per_block);
+    }
+    first[num_tables] = acc;
+  }
+  __syncthreads();
+  for (int b = threadIdx.x; b < nblocks; b += blockDim.x) {
+    SegBlock m{-1, 0, 0, 0, 0, 0, 0};
+    if (b < first[num_tables]) {
+      int lo = 0, hi = num_tables - 1;          // last table whose first block is <= b
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (first[mid] <= b) lo = mid; else hi = mid - 1;
+      }
+      const int64_t beg = start[lo] + (int64_t)(b - first[lo]) * per_block;
+      const int64_t end = beg + per_block < start[lo + 1] ? beg + per_block : start[lo + 1];
+      m = SegBlock{lo, first[lo], first[lo + 1], 0, start[lo], beg, end};
+    }
+    blk[b] = m;
+  }
 }
 
 // Exclusive scan of one uint32 per thread over a 256-thread block; returns the exclusive
@@ -95,7 +150,7 @@ template <bool ID64, typename K, bool B16>
 __global__ __launch_bounds__(kThreads) void form_keys_bags_kernel(
     const void* __restrict__ ids, int64_t n, const int64_t* __restrict__ offsets, int64_t batch,
     int64_t num_bags, const int64_t* __restrict__ row_base, int64_t modulus, uint64_t flip,
-    int parts, K* __restrict__ keys, void* __restrict__ bags) {
+    int parts, int seg_bits, K* __restrict__ keys, void* __restrict__ bags) {
   const int lane = threadIdx.x & 63;
   const int64_t wave = ((int64_t)blockIdx.x * kThreads + threadIdx.x) >> 6;
   const int64_t s0 = (wave / parts) * 64;
@@ -119,7 +174,8 @@ __global__ __launch_bounds__(kThreads) void form_keys_bags_kernel(
       const int64_t id = ID64 ? static_cast<const int64_t*>(ids)[i]
                               : (int64_t) static_cast<const int32_t*>(ids)[i];
       int64_t key = floor_mod(id, modulus);
-      if (row_base) key += row_base[bag / batch];
+      if (seg_bits) key = (int64_t)(((uint64_t)(bag / batch) << seg_bits) | (uint64_t)key);
+      else if (row_base) key += row_base[bag / batch];
       keys[i] = (K)((uint64_t)key ^ flip);
       if constexpr (B16)
         static_cast<uint16_t*>(bags)[i] = (uint16_t)(bag - (bag / batch) * batch);
@@ -148,24 +204,40 @@ __global__ __launch_bounds__(kThreads) void form_keys_flat_kernel(const void* __
 // (ld = block count rounded up to 4), so one digit's counts over the blocks are contiguous.
 constexpr int kUpU = 4;   // keys in flight per thread in the upsweep
 
+// Range of radix block b: the segment map's (table-segmented sort), else b * per_block.
+__device__ __forceinline__ void block_range(const SegBlock* blk, int64_t per_block, int64_t n,
+                                            int64_t* beg, int64_t* end) {
+  if (blk) {
+    const SegBlock& m = blk[blockIdx.x];
+    *beg = m.seg < 0 ? 0 : m.beg;
+    *end = m.seg < 0 ? 0 : m.end;
+  } else {
+    *beg = (int64_t)blockIdx.x * per_block;
+    *end = *beg + per_block < n ? *beg + per_block : n;
+  }
+}
+
 template <typename K>
 __global__ __launch_bounds__(kThreads) void radix_upsweep_kernel(
     const K* __restrict__ keys, int64_t n, int shift, int nbits, int64_t per_block,
-    uint32_t* __restrict__ hist, int ld) {
+    const SegBlock* __restrict__ blk, uint32_t* __restrict__ hist, int ld) {
   __shared__ uint32_t cnt[4][kBuckets];
   const int wave = threadIdx.x >> 6;
   for (int i = threadIdx.x; i < 4 * kBuckets; i += kThreads) (&cnt[0][0])[i] = 0;
   __syncthreads();
   const uint32_t mask = (1u << nbits) - 1u;
-  const int64_t beg = (int64_t)blockIdx.x * per_block;
-  const int64_t end = beg + per_block < n ? beg + per_block : n;
+  int64_t beg, end;
+  block_range(blk, per_block, n, &beg, &end);
   // Counting needs no order: LDS atomic adds into the wave's own bins (lanes of one wave
   // that share a digit are serialised by the LDS; waves never contend).  Keys are read as
-  // 16-byte vectors, kUpU per thread issued before any is counted; a range's last partial
-  // vector is read one key at a time.  (Block ranges start on multiples of 1024 keys.)
+  // 16-byte vectors, kUpU per thread issued before any is counted; the keys before the
+  // first 16-byte boundary of the range and after its last one are read one at a time.
   constexpr int V = 16 / (int)sizeof(K);
-  const int64_t vend = beg + ((end - beg) / V) * V;
-  for (int64_t base = beg; base < vend; base += (int64_t)kThreads * kUpU * V) {
+  const int64_t vbeg = ((beg + V - 1) / V) * V < end ? ((beg + V - 1) / V) * V : end;
+  const int64_t vend = vbeg + ((end - vbeg) / V) * V;
+  for (int64_t e = beg + threadIdx.x; e < vbeg; e += kThreads)
+    atomicAdd(&cnt[wave][(uint32_t)(keys[e] >> shift) & mask], 1u);
+  for (int64_t base = vbeg; base < vend; base += (int64_t)kThreads * kUpU * V) {
     uint4 raw[kUpU];
 #pragma unroll
     for (int j = 0; j < kUpU; ++j) {
@@ -217,10 +289,11 @@ __global__ __launch_bounds__(kThreads) void radix_scan_kernel(uint32_t* __restri
 }
 
 // --------------------------------------------------------------------------- downsweep
-template <typename K, int ITEMS>
+template <typename K, int ITEMS, bool B16>
 struct DownsweepSmem {
   K keys[kThreads * ITEMS];
   uint32_t vals[kThreads * ITEMS];
+  uint16_t bags[B16 ? kThreads * ITEMS : 2];
   uint32_t wcnt[4][kBuckets];
   uint32_t run[kBuckets];
   uint32_t tstart[kBuckets];
@@ -230,14 +303,21 @@ struct DownsweepSmem {
 
 // IDENT: payload of pass 0 is the element index.  FUSED: few blocks, so this block sums the
 // digit counts of the blocks before it itself instead of reading a separate scan's output.
-template <typename K, int ITEMS, bool IDENT, bool FUSED>
+// B16: a second payload, the occurrence's 16-bit sample index, rides along (pass 0 reads it
+// in occurrence order, which is the element order then).
+// blk (table-segmented sort): the block's table, range and first blocks; its digit
+// offsets are the table's first position plus prefixes within the table, read off the
+// global per-digit scan as differences from the table's first block.
+template <typename K, int ITEMS, bool IDENT, bool FUSED, bool B16>
 __global__ __launch_bounds__(kThreads) void radix_downsweep_kernel(
     const K* __restrict__ keys_in, const uint32_t* __restrict__ vals_in,
-    K* __restrict__ keys_out, uint32_t* __restrict__ vals_out, int64_t n, int shift,
-    int nbits, int64_t per_block, const uint32_t* __restrict__ hist,
-    const uint32_t* __restrict__ totals, int nblocks, int ld) {
+    const uint16_t* __restrict__ bags_in, K* __restrict__ keys_out,
+    uint32_t* __restrict__ vals_out, uint16_t* __restrict__ bags_out, int64_t n, int shift,
+    int nbits, int64_t per_block, const SegBlock* __restrict__ blk,
+    const uint32_t* __restrict__ hist, const uint32_t* __restrict__ totals, int nblocks,
+    int ld) {
   constexpr int kT = kThreads * ITEMS;
-  __shared__ DownsweepSmem<K, ITEMS> sm;
+  __shared__ DownsweepSmem<K, ITEMS, B16> sm;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const uint32_t mask = (1u << nbits) - 1u;
 
@@ -265,22 +345,30 @@ __global__ __launch_bounds__(kThreads) void radix_downsweep_kernel(
           before += g < me ? x : 0u;
         }
       }
+    } else if (blk) {
+      const SegBlock& m = blk[blockIdx.x];
+      const int64_t row = (int64_t)d * ld;
+      const uint32_t h0 = m.seg < 0 ? 0u : hist[row + m.first];
+      before = m.seg < 0 ? 0u : hist[row + blockIdx.x] - h0;
+      tot = m.seg < 0 ? 0u : (m.next < nblocks ? hist[row + m.next] : totals[d]) - h0;
     } else {
       tot = totals[d];
       before = hist[(int64_t)d * ld + blockIdx.x];
     }
     uint32_t all;
-    sm.run[d] = block_excl_scan_256(tot, sm.tmp, &all) + before;
+    const uint32_t base = blk ? (uint32_t)blk[blockIdx.x].seg_beg : 0u;
+    sm.run[d] = base + block_excl_scan_256(tot, sm.tmp, &all) + before;
   }
   __syncthreads();
 
-  const int64_t beg = (int64_t)blockIdx.x * per_block;
-  const int64_t end = beg + per_block < n ? beg + per_block : n;
+  int64_t beg, end;
+  block_range(blk, per_block, n, &beg, &end);
   const uint64_t lt = lanemask_lt();
 
   for (int64_t tile = beg; tile < end; tile += kT) {
     K key[ITEMS];
     uint32_t val[ITEMS];
+    uint16_t bag[ITEMS];
     uint32_t rank[ITEMS];
     bool valid[ITEMS];
 #pragma unroll
@@ -289,6 +377,7 @@ __global__ __launch_bounds__(kThreads) void radix_downsweep_kernel(
       valid[k] = e < end;
       key[k] = valid[k] ? keys_in[e] : (K)0;
       val[k] = valid[k] ? (IDENT ? (uint32_t)e : vals_in[e]) : 0u;
+      bag[k] = (B16 && valid[k]) ? bags_in[e] : (uint16_t)0;
     }
     for (int d = lane; d < kBuckets; d += 64) sm.wcnt[wave][d] = 0;
     __builtin_amdgcn_wave_barrier();
@@ -334,6 +423,7 @@ __global__ __launch_bounds__(kThreads) void radix_downsweep_kernel(
         const uint32_t pos = sm.tstart[d] + sm.wcnt[wave][d] + rank[k];
         sm.keys[pos] = key[k];
         sm.vals[pos] = val[k];
+        if constexpr (B16) sm.bags[pos] = bag[k];
       }
     }
     __syncthreads();
@@ -344,6 +434,7 @@ __global__ __launch_bounds__(kThreads) void radix_downsweep_kernel(
       const uint32_t o = sm.run[d] + (uint32_t)q - sm.tstart[d];
       keys_out[o] = kk;
       vals_out[o] = sm.vals[q];
+      if constexpr (B16) bags_out[o] = sm.bags[q];
     }
     __syncthreads();
     sm.run[threadIdx.x] += sm.tcount[threadIdx.x];
@@ -422,14 +513,15 @@ __global__ __launch_bounds__(1024) void heads_scan_kernel(uint32_t* __restrict__
 }
 
 // sorted_src[p] = (distinct-row index of position p, bag of its occurrence, key as two
-// words); bag_of (occurrence order) gives the bag, and without bags the occurrence is its
-// own bag.  Every load of the tile is issued first (keys, the key before each position,
+// words); bag_of gives the bag, and without bags the occurrence is its own bag.  Every load of the tile is issued first (keys, the key before each position,
 // occurrence, then the bags through the occurrences; and, when FUSED, the head counts of the
 // earlier tiles), then one barrier publishes the per-round wave head counts.
 // FUSED: few tiles, so the block sums the head counts of the tiles before it itself, and
 // the last block publishes U.
-// B16: bag_of holds 16-bit sample indices (form_keys_bags_kernel<.., true>); the bag is
-// table * batch + sample with the table the last one whose row_base is <= the key.
+// B16: bag_of holds the 16-bit sample indices (form_keys_bags_kernel<.., true>) carried
+// through the sort, in sorted order; the bag is table * batch + sample, the table taken from
+// the key.  Otherwise bag_of holds 32-bit bags in occurrence order, read through the
+// occurrence index.
 constexpr int kFinMaxTables = 1024;
 template <typename K, bool FUSED, bool B16>
 __global__ __launch_bounds__(kThreads) void unique_finalize_kernel(
@@ -437,7 +529,7 @@ __global__ __launch_bounds__(kThreads) void unique_finalize_kernel(
     int64_t n, uint64_t flip, const uint32_t* __restrict__ tile_heads, int64_t ntiles,
     int64_t* __restrict__ uniq, int32_t* __restrict__ inverse, int32_t* __restrict__ seg_offsets,
     int4* __restrict__ sorted_src, int32_t* __restrict__ num_unique,
-    const int64_t* __restrict__ row_base, int num_tables, int64_t batch) {
+    const int64_t* __restrict__ row_base, int num_tables, int64_t batch, int seg_bits) {
   __shared__ uint32_t wcnt[kFinRounds][4];
   __shared__ uint32_t wtile[2][4];
   __shared__ int64_t s_rb[B16 ? kFinMaxTables : 1];
@@ -463,11 +555,11 @@ __global__ __launch_bounds__(kThreads) void unique_finalize_kernel(
 #pragma unroll
   for (int j = 0; j < kFinRounds; ++j) {
     const int64_t p = t0 + (int64_t)j * kThreads + threadIdx.x;
-    const bool ok = p < n && bag_of && occ[j] < (uint64_t)n;
-    if constexpr (B16)
-      bag[j] = ok ? (uint32_t) static_cast<const uint16_t*>(bag_of)[occ[j]] : occ[j];
-    else
-      bag[j] = ok ? static_cast<const uint32_t*>(bag_of)[occ[j]] : occ[j];
+    if constexpr (B16)             // sorted with the keys: position order
+      bag[j] = (p < n && bag_of) ? (uint32_t) static_cast<const uint16_t*>(bag_of)[p] : occ[j];
+    else                           // occurrence order: read through the occurrence
+      bag[j] = (p < n && bag_of && occ[j] < (uint64_t)n)
+                   ? static_cast<const uint32_t*>(bag_of)[occ[j]] : occ[j];
   }
   uint32_t before_tile = 0, all_tiles = 0;
   if (FUSED) {
@@ -513,7 +605,12 @@ __global__ __launch_bounds__(kThreads) void unique_finalize_kernel(
     base += wcnt[j][0] + wcnt[j][1] + wcnt[j][2] + wcnt[j][3];
     if (p < n) {
       const uint32_t r = before + (uint32_t)__popcll(m[j] & le) - 1u;   // heads <= p, less one
-      const uint64_t kk = (uint64_t)key[j] ^ flip;
+      uint64_t kk = (uint64_t)key[j] ^ flip;
+      int seg = -1;                              // table-segmented sort: (t << L) | local
+      if (seg_bits) {
+        seg = (int)(kk >> seg_bits) < num_tables ? (int)(kk >> seg_bits) : num_tables - 1;
+        kk = (uint64_t)row_base[seg] + (kk & ((1ull << seg_bits) - 1ull));
+      }
       if ((m[j] >> lane) & 1ull) {
         uniq[r] = (int64_t)kk;
         if (seg_offsets) seg_offsets[r] = (int32_t)p;
@@ -522,7 +619,11 @@ __global__ __launch_bounds__(kThreads) void unique_finalize_kernel(
       if (sorted_src) {
         uint32_t bg = bag[j];
         if constexpr (B16) {
-          int lo = 0, hi = num_tables - 1;       // last table whose first row is <= the key
+          int lo = seg, hi = seg;                // the table: from the key, else the last one
+          if (seg < 0) {                         // whose first row is <= the key
+            lo = 0;
+            hi = num_tables - 1;
+          }
           while (lo < hi) {
             const int mid = (lo + hi + 1) >> 1;
             if ((uint64_t)s_rb[mid] <= kk) lo = mid; else hi = mid - 1;
@@ -549,10 +650,12 @@ struct UniqueWs {
   void* keys_b;
   uint32_t* vals_a;
   uint32_t* vals_b;
-  uint32_t* bags_a;           // bag of each occurrence, occurrence order
+  uint32_t* bags_a;           // bag of each occurrence, occurrence order (or 16-bit ones)
+  uint16_t* bags16_b;         // the 16-bit sample indices' second buffer
   uint32_t* hist;
   uint32_t* totals;
   uint32_t* tile_heads;
+  SegBlock* blk;              // the table-segmented sort's block map
   size_t bytes;
 };
 
@@ -570,69 +673,104 @@ UniqueWs carve(void* base, int64_t n) {
   w.vals_a = reinterpret_cast<uint32_t*>(take(sizeof(uint32_t) * (size_t)n));
   w.vals_b = reinterpret_cast<uint32_t*>(take(sizeof(uint32_t) * (size_t)n));
   w.bags_a = reinterpret_cast<uint32_t*>(take(sizeof(uint32_t) * (size_t)n));
+  w.bags16_b = reinterpret_cast<uint16_t*>(take(sizeof(uint16_t) * (size_t)n));
   w.hist = reinterpret_cast<uint32_t*>(take(sizeof(uint32_t) * kBuckets * kMaxBlocks));
   w.totals = reinterpret_cast<uint32_t*>(take(sizeof(uint32_t) * kBuckets));
   w.tile_heads = reinterpret_cast<uint32_t*>(
       take(sizeof(uint32_t) * (size_t)((n + kFinTile - 1) / kFinTile + 1)));
+  w.blk = reinterpret_cast<SegBlock*>(take(sizeof(SegBlock) * kMaxBlocks));
   w.bytes = off;
   return w;
 }
 
 template <typename K, int ITEMS>
-void radix_pass(bool first, const K* kin, const uint32_t* vin, K* kout, uint32_t* vout,
-                int64_t n, int shift, int nbits, int64_t per_block, uint32_t* hist,
-                uint32_t* totals, int nblocks, hipStream_t s) {
+void radix_pass(bool first, const K* kin, const uint32_t* vin, const uint16_t* bin, K* kout,
+                uint32_t* vout, uint16_t* bout, int64_t n, int shift, int nbits,
+                int64_t per_block, const SegBlock* blk, uint32_t* hist, uint32_t* totals,
+                int nblocks, hipStream_t s) {
   const int ld = (nblocks + 3) & ~3;
-  radix_upsweep_kernel<K><<<nblocks, kThreads, 0, s>>>(kin, n, shift, nbits, per_block, hist,
-                                                       ld);
-  const bool fused = nblocks <= kFusedScanBlocks;
+  radix_upsweep_kernel<K><<<nblocks, kThreads, 0, s>>>(kin, n, shift, nbits, per_block, blk,
+                                                       hist, ld);
+  const bool fused = nblocks <= kFusedScanBlocks && !blk;
   if (!fused) radix_scan_kernel<<<kBuckets, kThreads, 0, s>>>(hist, nblocks, ld, totals);
-#define CTR_DS(I, FU)                                                                      \
-  radix_downsweep_kernel<K, ITEMS, I, FU><<<nblocks, kThreads, 0, s>>>(                    \
-      kin, vin, kout, vout, n, shift, nbits, per_block, hist, totals, nblocks, ld)
+#define CTR_DS(I, FU, B)                                                                   \
+  radix_downsweep_kernel<K, ITEMS, I, FU, B><<<nblocks, kThreads, 0, s>>>(                 \
+      kin, vin, bin, kout, vout, bout, n, shift, nbits, per_block, blk, hist, totals, nblocks, \
+      ld)
+#define CTR_DS2(I, FU) \
+  if (bin) CTR_DS(I, FU, true); else CTR_DS(I, FU, false)
   if (first) {
-    if (fused) CTR_DS(true, true); else CTR_DS(true, false);
+    if (fused) { CTR_DS2(true, true); } else { CTR_DS2(true, false); }
   } else {
-    if (fused) CTR_DS(false, true); else CTR_DS(false, false);
+    if (fused) { CTR_DS2(false, true); } else { CTR_DS2(false, false); }
   }
+#undef CTR_DS2
 #undef CTR_DS
 }
 
+// seg: the table-segmented sort (key_bits = the local bits): blocks are cut per table by
+// seg_blocks_kernel into `blk`, at most one partial block per table.
+struct SegPlan {
+  const int64_t* offsets;
+  int64_t batch;
+  int num_tables;
+  SegBlock* blk;
+};
+
+// bags_a/bags_b (may be null): the 16-bit sample indices, in occurrence order in bags_a,
+// carried along; *sb receives the buffer that holds them in sorted order.
 template <typename K, int ITEMS>
-void radix_sort(int key_bits, K* keys_a, K* keys_b, uint32_t* vbuf0, uint32_t* vbuf1, int64_t n,
-                uint32_t* hist, uint32_t* totals, const K** sk, const uint32_t** sv,
+void radix_sort(int key_bits, K* keys_a, K* keys_b, uint32_t* vbuf0, uint32_t* vbuf1,
+                uint16_t* bags_a, uint16_t* bags_b, int64_t n, uint32_t* hist, uint32_t* totals,
+                const K** sk, const uint32_t** sv, const uint16_t** sb, const SegPlan* seg,
                 hipStream_t s) {
   constexpr int kT = kThreads * ITEMS;
   const int64_t ntiles = (n + kT - 1) / kT;
-  int nblocks = (int)(ntiles < kMaxBlocks ? ntiles : kMaxBlocks);
-  const int64_t tiles_per_block = (ntiles + nblocks - 1) / nblocks;
-  nblocks = (int)((ntiles + tiles_per_block - 1) / tiles_per_block);
-  const int64_t per_block = tiles_per_block * kT;
+  int nblocks, spare = seg ? seg->num_tables : 0;   // a partial block per table at most
+  int64_t per_block;
+  {
+    const int64_t avail = kMaxBlocks - spare;
+    int64_t nb = ntiles < avail ? ntiles : avail;
+    const int64_t tiles_per_block = (ntiles + nb - 1) / nb;
+    nb = (ntiles + tiles_per_block - 1) / tiles_per_block;
+    per_block = tiles_per_block * kT;
+    nblocks = (int)(nb + spare);
+  }
+  const SegBlock* blk = nullptr;
+  if (seg) {
+    seg_blocks_kernel<<<1, 1024, 0, s>>>(seg->offsets, seg->batch, seg->num_tables, n, per_block,
+                                         nblocks, seg->blk);
+    blk = seg->blk;
+  }
   const int passes = (key_bits + kMaxBits - 1) / kMaxBits;
   K* kin = keys_a;
   K* kout = keys_b;
   uint32_t* vb[2] = {vbuf0, vbuf1};
   const uint32_t* vin = nullptr;
+  uint16_t* bin = bags_a;
+  uint16_t* bout = bags_b;
   int shift = 0;
   for (int p = 0; p < passes; ++p) {
     const int left = key_bits - shift;
     const int nbits = (left + (passes - p) - 1) / (passes - p);   // spread bits evenly
     uint32_t* vout = vb[(passes - 1 - p) & 1];                       // last pass -> vbuf0
-    radix_pass<K, ITEMS>(p == 0, kin, vin, kout, vout, n, shift, nbits, per_block, hist, totals,
-                         nblocks, s);
+    radix_pass<K, ITEMS>(p == 0, kin, vin, bin, kout, vout, bout, n, shift, nbits, per_block,
+                         blk, hist, totals, nblocks, s);
     shift += nbits;
     vin = vout;
     std::swap(kin, kout);
+    std::swap(bin, bout);
   }
   *sk = kin;
   *sv = vin;
+  *sb = bin;
 }
 
 template <typename K>
 hipError_t unique_impl(const void* ids, bool ids64, int64_t n, const int64_t* offsets,
                        int64_t batch, int32_t num_tables, const int64_t* row_base,
-                       int64_t modulus, int key_bits, uint64_t flip, int64_t* uniq,
-                       int32_t* inverse, int32_t* num_unique, int32_t* perm,
+                       int64_t modulus, int key_bits, int seg_bits, uint64_t flip,
+                       int64_t* uniq, int32_t* inverse, int32_t* num_unique, int32_t* perm,
                        int32_t* seg_offsets, int4* sorted_src, UniqueWs& w, hipStream_t s) {
   const bool bags = offsets != nullptr && sorted_src != nullptr;
   // 16-bit sample indices for the bags when the table can be told from the key
@@ -654,7 +792,8 @@ hipError_t unique_impl(const void* ids, bool ids64, int64_t n, const int64_t* of
     if (blocks > 0) {
 #define CTR_FK(I64, B)                                                                     \
   form_keys_bags_kernel<I64, K, B><<<(unsigned)blocks, kThreads, 0, s>>>(                  \
-      ids, n, offsets, batch, num_bags, row_base, modulus, flip, (int)parts, keys_a, w.bags_a)
+      ids, n, offsets, batch, num_bags, row_base, modulus, flip, (int)parts, seg_bits, keys_a, \
+      w.bags_a)
       if (ids64) {
         if (b16) CTR_FK(true, true); else CTR_FK(true, false);
       } else {
@@ -680,11 +819,22 @@ hipError_t unique_impl(const void* ids, bool ids64, int64_t n, const int64_t* of
   uint32_t* vbuf1 = perm ? w.vals_a : w.vals_b;
   const K* sk;
   const uint32_t* sv;
+  const SegPlan plan{offsets, batch, num_tables, w.blk};
+  const SegPlan* seg = seg_bits ? &plan : nullptr;      // sort the local bits per table
+  const int sort_bits = seg_bits ? seg_bits : key_bits;
+  // 16-bit sample indices ride along through the passes; 32-bit bags stay in occurrence
+  // order for the finalize to read through the occurrence index
+  uint16_t* b16a = b16 ? reinterpret_cast<uint16_t*>(w.bags_a) : nullptr;
+  uint16_t* b16b = b16 ? w.bags16_b : nullptr;
+  const uint16_t* sb16 = nullptr;
   if (n <= (1 << 20))   // small batches: shorter tiles, more blocks, shorter chains
-    radix_sort<K, 4>(key_bits, keys_a, keys_b, vbuf0, vbuf1, n, w.hist, w.totals, &sk, &sv, s);
+    radix_sort<K, 4>(sort_bits, keys_a, keys_b, vbuf0, vbuf1, b16a, b16b, n, w.hist, w.totals,
+                     &sk, &sv, &sb16, seg, s);
   else
-    radix_sort<K, 8>(key_bits, keys_a, keys_b, vbuf0, vbuf1, n, w.hist, w.totals, &sk, &sv, s);
-  const void* sb = bags ? w.bags_a : nullptr;   // bag of each occurrence, occurrence order
+    radix_sort<K, 8>(sort_bits, keys_a, keys_b, vbuf0, vbuf1, b16a, b16b, n, w.hist, w.totals,
+                     &sk, &sv, &sb16, seg, s);
+  const void* sb = !bags ? nullptr : b16 ? static_cast<const void*>(sb16)
+                                         : static_cast<const void*>(w.bags_a);
 
   // finalize: heads, their scan, and the scatter of uniq / seg / inverse / sorted_src
   const int64_t ftiles = (n + kFinTile - 1) / kFinTile;
@@ -692,7 +842,7 @@ hipError_t unique_impl(const void* ids, bool ids64, int64_t n, const int64_t* of
 #define CTR_FIN(FU, B)                                                                     \
   unique_finalize_kernel<K, FU, B><<<(unsigned)ftiles, kThreads, 0, s>>>(                  \
       sk, sv, sb, n, flip, w.tile_heads, ftiles, uniq, inverse, seg_offsets, sorted_src,   \
-      num_unique, row_base, num_tables, batch)
+      num_unique, row_base, num_tables, batch, seg_bits)
   if (ftiles <= kFusedHeadTiles) {
     if (b16) CTR_FIN(true, true); else CTR_FIN(true, false);
   } else {
@@ -709,8 +859,8 @@ size_t unique_workspace_bytes(int64_t n) { return carve(nullptr, n).bytes; }
 
 hipError_t launch_unique(const void* ids, bool ids64, int64_t n, const int64_t* offsets,
                          int64_t batch, int32_t num_tables, const int64_t* row_base,
-                         int64_t modulus, int key_bits, bool key_signed, int64_t* uniq,
-                         int32_t* inverse, int32_t* num_unique, int32_t* perm,
+                         int64_t modulus, int key_bits, int seg_bits, bool key_signed,
+                         int64_t* uniq, int32_t* inverse, int32_t* num_unique, int32_t* perm,
                          int32_t* seg_offsets, int4* sorted_src, void* workspace,
                          hipStream_t s) {
   if (n == 0) {
@@ -719,13 +869,14 @@ hipError_t launch_unique(const void* ids, bool ids64, int64_t n, const int64_t* 
   }
   UniqueWs w = carve(workspace, n);
   const uint64_t flip = key_signed ? (1ull << 63) : 0ull;
-  // 32-bit keys whenever the live key range fits (a quarter less sort traffic)
-  if (!key_signed && key_bits <= 32)
+  // 32-bit keys whenever the live key range fits (a quarter less sort traffic); the
+  // table-segmented sort's (t << L) | local always does (the caller checked)
+  if (seg_bits || (!key_signed && key_bits <= 32))
     return unique_impl<uint32_t>(ids, ids64, n, offsets, batch, num_tables, row_base, modulus,
-                                 key_bits, flip, uniq, inverse, num_unique, perm, seg_offsets,
-                                 sorted_src, w, s);
+                                 key_bits, seg_bits, flip, uniq, inverse, num_unique, perm,
+                                 seg_offsets, sorted_src, w, s);
   return unique_impl<uint64_t>(ids, ids64, n, offsets, batch, num_tables, row_base, modulus,
-                               key_bits, flip, uniq, inverse, num_unique, perm, seg_offsets,
+                               key_bits, 0, flip, uniq, inverse, num_unique, perm, seg_offsets,
                                sorted_src, w, s);
 }
 

@@ -56,7 +56,7 @@ class CtrStep(ctypes.Structure):
                 ("sorted_src", _P * 3), ("rounding", ctypes.c_int32),
                 ("sr_seed", ctypes.c_uint64), ("grad_dtype", ctypes.c_int32),
                 ("ws_unique2", _P), ("ws_unique2_bytes", ctypes.c_size_t),
-                ("mark_stage", ctypes.c_int32)]
+                ("mark_stage", ctypes.c_int32), ("max_table_rows", ctypes.c_int64)]
 
 _lib = None
 
@@ -87,7 +87,8 @@ def load() -> ctypes.CDLL:
         "ctr_version": (i32, []),
         "ctr_status_string": (ctypes.c_char_p, [i32]),
         "ctr_last_error": (ctypes.c_char_p, []),
-        "ctr_unique_ids": (i32, [P, i32, i64, P, i64, i32, P, i64, i64, P, P, P, P, P, P, P, PS, P]),
+        "ctr_unique_ids": (i32, [P, i32, i64, P, i64, i32, P, i64, i64, i64, P, P, P, P, P, P, P,
+                                 PS, P]),
         "ctr_gather_rows": (i32, [P, i32, i64, i32, P, P, i64, P, P]),
         "ctr_embbag_fwd": (i32, [P, i32, i64, i32, P, i32, P, i32, i64, P, i64, P, i64, i64, P]),
         "ctr_embbag_bwd": (i32, [P, i64, i64, P, i64, i32, i32, i64, P, P, P, P, P, P, PS, P]),
@@ -195,7 +196,7 @@ def _workspace(nbytes: int, device) -> torch.Tensor:
 def unique_workspace_bytes(n: int) -> int:
     """Workspace of ctr_unique_ids for n occurrences (the library's two-call query)."""
     wsb = ctypes.c_size_t(0)
-    _check("ctr_unique_ids", load().ctr_unique_ids(None, CTR_I64, n, None, 0, 0, None, 0, 0,
+    _check("ctr_unique_ids", load().ctr_unique_ids(None, CTR_I64, n, None, 0, 0, None, 0, 0, 0,
                                                    None, None, None, None, None, None, None,
                                                    ctypes.byref(wsb), None))
     return wsb.value
@@ -217,7 +218,8 @@ def ctr_version() -> int:
 
 def ctr_unique_ids(ids: torch.Tensor, *, offsets: Optional[torch.Tensor] = None, batch: int = 0,
                    num_tables: int = 0, row_base: Optional[torch.Tensor] = None,
-                   total_rows: int = 0, key_modulus: int = 0, want_perm: bool = True,
+                   total_rows: int = 0, max_table_rows: int = 0, key_modulus: int = 0,
+                   want_perm: bool = True,
                    want_seg: bool = True, workspace: Optional[torch.Tensor] = None,
                    out: Optional[tuple] = None, sorted_src: Optional[torch.Tensor] = None,
                    stream=None, prepare: bool = False
@@ -239,7 +241,7 @@ def ctr_unique_ids(ids: torch.Tensor, *, offsets: Optional[torch.Tensor] = None,
         perm = torch.empty(max(n, 1), dtype=torch.int32, device=dev) if want_perm else None
         seg = torch.empty(n + 1, dtype=torch.int32, device=dev) if want_seg else None
     args = (_ptr(ids), _index_code(ids), n, _ptr(offsets), batch, num_tables, _ptr(row_base),
-            total_rows, key_modulus)
+            total_rows, max_table_rows, key_modulus)
     if workspace is None:
         workspace = _workspace(unique_workspace_bytes(n), dev)
     ws = workspace

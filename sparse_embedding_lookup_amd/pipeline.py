@@ -141,8 +141,8 @@ class FrontEnd:
             F = w.F
             self._c_unique = ctr.ctr_unique_ids(
                 self.indices, offsets=self.offsets, batch=w.batch, num_tables=w.num_tables,
-                row_base=self.row_base, total_rows=w.total_rows, workspace=self.ws_unique,
-                out=self._unique_out, sorted_src=self.sorted_src, **P)
+                row_base=self.row_base, total_rows=w.total_rows, max_table_rows=max(w.rows),
+                workspace=self.ws_unique, out=self._unique_out, sorted_src=self.sorted_src, **P)
             self._c_embbag_fwd = ctr.ctr_embbag_fwd(
                 self.table, self.indices, self.offsets, w.batch, w.num_tables, self.Z[:, 1:, :],
                 F * d, d, row_base=self.row_base, **P)
@@ -413,6 +413,7 @@ class FrontEnd:
         d.indices, d.nnz, d.offsets = P(self.indices), self.nnz, P(self.offsets)
         d.batch, d.num_tables, d.dim = w.batch, w.num_tables, w.dim
         d.row_base, d.key_modulus = P(self.row_base), w.key_modulus
+        d.max_table_rows = max(w.rows) if w.interaction else 0
         d.table, d.dtype, d.compute = P(self.table), ctr._dtype_code(self.table), self.compute
         d.total_rows, d.lr = w.total_rows, w.lr
         d.rounding = (ctr.CTR_ROUND_STOCHASTIC if self.rounding == "stochastic"

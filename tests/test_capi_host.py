@@ -59,27 +59,31 @@ def test_status_strings_and_version():
 def test_unique_workspace_query_and_bad_args():
     lib = _lib()
     wsb = ctypes.c_size_t(0)
-    assert lib.ctr_unique_ids(None, 1, 1000, None, 0, 0, None, 0, 0, None, None, None, None,
+    assert lib.ctr_unique_ids(None, 1, 1000, None, 0, 0, None, 0, 0, 0, None, None, None, None,
                               None, None, None, ctypes.byref(wsb), None) == ctr.CTR_OK
     assert wsb.value >= 1000 * 24
     bad = ctypes.c_size_t(10)
-    st = lib.ctr_unique_ids(FAKE, 1, 1000, None, 0, 0, None, 0, 0, FAKE, FAKE, FAKE, None, None,
+    st = lib.ctr_unique_ids(FAKE, 1, 1000, None, 0, 0, None, 0, 0, 0, FAKE, FAKE, FAKE, None, None,
                             None, FAKE, ctypes.byref(bad), None)
     assert st == ctr.CTR_ERR_WORKSPACE_TOO_SMALL
     big = ctypes.c_size_t(wsb.value)
-    st = lib.ctr_unique_ids(FAKE, 1, 1000, None, 0, 0, None, 0, 0, FAKE, FAKE, FAKE, None, None,
+    st = lib.ctr_unique_ids(FAKE, 1, 1000, None, 0, 0, None, 0, 0, 0, FAKE, FAKE, FAKE, None, None,
                             None, MISALIGNED, ctypes.byref(big), None)
     assert st == ctr.CTR_ERR_UNSUPPORTED and b"aligned" in lib.ctr_last_error()
-    assert lib.ctr_unique_ids(FAKE, 1, -1, None, 0, 0, None, 0, 0, None, None, None, None, None,
+    assert lib.ctr_unique_ids(FAKE, 1, -1, None, 0, 0, None, 0, 0, 0, None, None, None, None, None,
                               None, None, ctypes.byref(wsb), None) == ctr.CTR_ERR_INVALID_ARGUMENT
-    assert lib.ctr_unique_ids(FAKE, 1, 2 ** 31, None, 0, 0, None, 0, 0, None, None, None, None,
+    assert lib.ctr_unique_ids(FAKE, 1, 2 ** 31, None, 0, 0, None, 0, 0, 0, None, None, None, None,
                               None, None, None, ctypes.byref(wsb), None) == ctr.CTR_ERR_INVALID_ARGUMENT
-    assert lib.ctr_unique_ids(FAKE, 7, 10, None, 0, 0, None, 0, 0, None, None, None, None, None,
+    assert lib.ctr_unique_ids(FAKE, 7, 10, None, 0, 0, None, 0, 0, 0, None, None, None, None, None,
                               None, None, ctypes.byref(wsb), None) == ctr.CTR_ERR_INVALID_ARGUMENT
     # row_base without offsets
-    assert lib.ctr_unique_ids(FAKE, 1, 10, None, 4, 2, FAKE, 100, 0, None, None, None, None, None,
+    assert lib.ctr_unique_ids(FAKE, 1, 10, None, 4, 2, FAKE, 100, 0, 0, None, None, None, None, None,
                               None, None, ctypes.byref(wsb), None) == ctr.CTR_ERR_INVALID_ARGUMENT
     assert b"offsets" in lib.ctr_last_error()
+    # a negative largest-table hint
+    assert lib.ctr_unique_ids(FAKE, 1, 10, FAKE, 4, 2, FAKE, 100, -1, 0, None, None, None, None,
+                              None, None, None, ctypes.byref(wsb), None) == \
+        ctr.CTR_ERR_INVALID_ARGUMENT
 
 
 def test_embbag_fwd_bad_args():
@@ -390,3 +394,11 @@ def test_noalloc_backward_limits_and_rejections():
     bad = list(args)
     bad[16] = 9                                                # unknown rounding
     assert lib.ctr_embbag_bwd_sgd_noalloc(*bad) == 1
+
+
+def test_binding_workspace_queries():
+    """The binding's two-call size queries run on the host (no device memory touched)."""
+    _lib()
+    assert ctr.unique_workspace_bytes(1000) >= 1000 * 16
+    assert ctr.unique_workspace_bytes(2_000_000) > ctr.unique_workspace_bytes(1000)
+    assert ctr.embbag_bwd_workspace_bytes(1000, 64) > 0

@@ -79,6 +79,25 @@ def _unique_cases():
     w = workloads.small(batch=512)
     cases["small_tables"] = (w.indices, dict(offsets=w.offsets, batch=w.batch, T=w.num_tables,
                                              rows=w.rows))
+    # tables as segments (the hint max_table_rows): fewer local bits than global ones
+    w = workloads.large(batch=512, tables=8)                    # 25 -> 22 bits, 131k ids
+    cases["large_t8_b512"] = (w.indices, dict(offsets=w.offsets, batch=w.batch,
+                                              T=w.num_tables, rows=w.rows))
+    w = workloads.large(batch=8192, tables=8)                   # 2.1M ids (wide tiles)
+    cases["large_t8_b8192"] = (w.indices, dict(offsets=w.offsets, batch=w.batch,
+                                               T=w.num_tables, rows=w.rows))
+    w = workloads.criteo(batch=1024)                            # 25 -> 24 bits, uneven tables
+    cases["criteo_b1024"] = (w.indices, dict(offsets=w.offsets, batch=w.batch,
+                                             T=w.num_tables, rows=w.rows))
+    # tiny tables, a table with no occurrences, two 2^24-row tables (25 -> 24 bits)
+    rows = [5, 16_000_000, 1, 70_000, 16_000_000, 3]
+    T, B = len(rows), 700
+    lengths = rng.integers(0, 9, size=(T, B))
+    lengths[2] = 0
+    off = np.zeros(T * B + 1, dtype=np.int64)
+    off[1:] = np.cumsum(lengths.reshape(-1))
+    ids = np.concatenate([rng.integers(0, rows[t], int(lengths[t].sum())) for t in range(T)])
+    cases["uneven_tables"] = (ids.astype(np.int64), dict(offsets=off, batch=B, T=T, rows=rows))
     ids = workloads.unbounded_zipf_capped(rng, 1.2, 10 ** 11, 300_001)
     cases["tensornet_mod"] = (ids, dict(modulus=20_000_000))
     cases["raw_signed"] = (rng.integers(-2 ** 62, 2 ** 62, size=70_001), {})
@@ -95,17 +114,24 @@ def _unique_cases():
 UNIQUE_CASES = _unique_cases()
 
 
-@pytest.mark.parametrize("name", list(UNIQUE_CASES))
-def test_unique_matches_oracle(name):
+TABLE_CASES = [k for k, (_, kw) in UNIQUE_CASES.items() if "offsets" in kw]
+UNIQUE_RUNS = [(k, False) for k in UNIQUE_CASES] + [(k, True) for k in TABLE_CASES]
+
+
+@pytest.mark.parametrize("name,hint", UNIQUE_RUNS)
+def test_unique_matches_oracle(name, hint):
+    """hint: the caller gives the largest table's rows, so the sort may run per table over the
+    local row bits (where that takes fewer passes)."""
     ids, kw = UNIQUE_CASES[name]
-    say("unique", name, ids.shape, kw.keys())
+    say("unique", name, "hint" if hint else "", ids.shape, kw.keys())
     n = ids.size
     if "offsets" in kw:
         rb = np.zeros(len(kw["rows"]) + 1, dtype=np.int64)
         rb[1:] = np.cumsum(kw["rows"])
         keys = orc.form_keys(ids, kw["offsets"], kw["T"], kw["batch"], rb)
         res = ctr.ctr_unique_ids(dev(ids), offsets=dev(kw["offsets"]), batch=kw["batch"],
-                                 num_tables=kw["T"], row_base=dev(rb), total_rows=int(rb[-1]))
+                                 num_tables=kw["T"], row_base=dev(rb), total_rows=int(rb[-1]),
+                                 max_table_rows=max(kw["rows"]) if hint else 0)
     else:
         m = kw.get("modulus", 0)
         keys = orc.form_keys(ids.astype(np.int64), np.array([0, n]), 1, 1, None, m)
@@ -120,13 +146,16 @@ def test_unique_matches_oracle(name):
     np.testing.assert_array_equal(seg[:U + 1], os_)
 
 
-@pytest.mark.parametrize("name", ["tiny_tables", "small_tables", "tensornet_mod", "all_equal",
-                                  "raw_signed"])
-def test_unique_sorted_src(name):
+@pytest.mark.parametrize("name,hint", [("tiny_tables", False), ("small_tables", False),
+                                       ("tensornet_mod", False), ("all_equal", False),
+                                       ("raw_signed", False), ("large_t8_b8192", True),
+                                       ("criteo_b1024", True), ("uneven_tables", True),
+                                       ("large_t8_b512", False)])
+def test_unique_sorted_src(name, hint):
     """(u, bag, key) per sorted position: u = inverse[perm[p]], bag = bag holding perm[p] (or
     the occurrence itself without bags), key = uniq[u] as two int32 words."""
     ids, kw = UNIQUE_CASES[name]
-    say("unique sorted_src", name)
+    say("unique sorted_src", name, "hint" if hint else "")
     n = ids.size
     src = torch.empty((n, 4), dtype=torch.int32, device=DEV)
     if "offsets" in kw:
@@ -135,7 +164,7 @@ def test_unique_sorted_src(name):
         keys = orc.form_keys(ids, kw["offsets"], kw["T"], kw["batch"], rb)
         ctr.ctr_unique_ids(dev(ids), offsets=dev(kw["offsets"]), batch=kw["batch"],
                            num_tables=kw["T"], row_base=dev(rb), total_rows=int(rb[-1]),
-                           sorted_src=src)
+                           max_table_rows=max(kw["rows"]) if hint else 0, sorted_src=src)
         bag_of = np.searchsorted(kw["offsets"], np.arange(n), side="right") - 1
     else:
         m = kw.get("modulus", 0)
