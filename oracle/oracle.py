@@ -19,6 +19,9 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
+# ORACLE_LIB names another, already built, copy of oracle.c to load instead (a sanitizer
+# build, for the host-side tests); build() always makes the default one.
+_LOAD = os.environ.get("ORACLE_LIB")
 _lib = None
 
 
@@ -36,8 +39,11 @@ def _load():
     global _lib
     if _lib is not None:
         return _lib
-    build()
-    lib = ctypes.CDLL(_LIB)
+    if _LOAD:
+        lib = ctypes.CDLL(_LOAD)
+    else:
+        build()
+        lib = ctypes.CDLL(_LIB)
     P = ctypes.c_void_p
     i32, i64, u64, f32, f64 = (ctypes.c_int32, ctypes.c_int64, ctypes.c_uint64,
                                ctypes.c_float, ctypes.c_double)

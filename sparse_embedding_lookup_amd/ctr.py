@@ -13,7 +13,9 @@ from typing import Optional, Sequence, Tuple
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libctr.so")
+# CTR_LIB names another build of the library (a sanitizer build of its host code, for the
+# host-side tests); the default is the in-tree libctr.so.  A missing library always raises.
+LIB_PATH = os.environ.get("CTR_LIB") or os.path.join(_HERE, "libctr.so")
 
 CTR_OK, CTR_ERR_INVALID_ARGUMENT, CTR_ERR_UNSUPPORTED, CTR_ERR_WORKSPACE_TOO_SMALL, CTR_ERR_HIP = range(5)
 CTR_F32, CTR_BF16 = 0, 1
