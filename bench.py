@@ -499,7 +499,7 @@ def bench_dictionary(args):
     n, d = w.nnz, w.dim
     cap = ctr.dict_capacity(w.entries)
     table = torch.empty((w.entries, d), dtype=torch.float32, device="cuda")
-    ctr.ctr_init_table_hash(table, [w.entries], w.table_seed)
+    ctr.ctr_init_tables_hash(table, [w.entries], w.table_seed)
     rows_dev = torch.from_numpy(w.dict_rows[:w.hot].astype(np.int64)).cuda()
     hot_rows = table[rows_dev].contiguous()
     slots, status = ctr.ctr_dict_build(torch.from_numpy(w.dict_keys).cuda(),

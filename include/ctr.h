@@ -27,7 +27,7 @@
  *     or too large size, F < 2, stride smaller than the row), CTR_ERR_UNSUPPORTED (pointer
  *     not 16-byte aligned, dim not a multiple of the 16-byte vector, dim or F beyond the
  *     kernel's limits), CTR_ERR_WORKSPACE_TOO_SMALL.  A launch failure returns CTR_ERR_HIP.
- *     ctr_last_error() gives a thread-local text of the last failure.
+ *     ctr_last_error_message() gives a thread-local text of the last failure.
  *   - Sizes that index elements must be < 2^31 (n, nnz, number of bags).
  *   - Data preconditions (0 <= index < rows of its table, offsets non-decreasing from 0 to
  *     nnz) are not checked on the hot path; ctr_validate_csr checks them.  Kernels clamp
@@ -71,7 +71,7 @@ int32_t ctr_version(void);
 const char* ctr_status_string(int32_t status);
 
 /* Thread-local text of the last failure in this thread ("" if none). */
-const char* ctr_last_error(void);
+const char* ctr_last_error_message(void);
 
 /*
  * ctr_unique_ids -- [TN] "Core Optimizations": collect the batch's IDs, sort them and give
@@ -159,42 +159,35 @@ int32_t ctr_embbag_bwd(const float* grad, int64_t grad_stride_b, int64_t grad_st
  * ctr_embbag_bwd_sgd -- ctr_embbag_bwd and ctr_sparse_sgd in one pass: the moment the
  * reduce-by-key completes the gradient of distinct row u it applies
  *   table[uniq[u], :] = round(table[uniq[u], :] - lr * g[u, :])
- * with exactly the arithmetic of ctr_sparse_sgd (so the table ends bit-identical to the
- * two-call path), without writing g to memory and reading it back.  row_grads is optional
- * (NULL: gradients are not kept).  Grouping and table rows from ctr_unique_ids' sorted_src
- * (u, bag, key); uniq serves the rows of segments that span several chunks.
- * dtype/total_rows/dim describe the table as in ctr_sparse_sgd; dim <= 1024.  Workspace:
- * two-call query, same size as ctr_embbag_bwd.
+ * with exactly the arithmetic of ctr_sparse_sgd with the same rounding and seed (so the table
+ * ends bit-identical to the two-call path), without writing g to memory and reading it back.
+ * Grouping and table rows come from ctr_unique_ids' sorted_src (u, bag, key); uniq serves the
+ * rows of segments that span several chunks.
+ *   grad: grad_dtype elements, CTR_F32 or CTR_BF16 (widened exactly; the sums stay fp32),
+ *         8-byte aligned for bf16, 16-byte for fp32; strides in elements as in ctr_embbag_bwd.
+ *   table: dtype/total_rows/dim as in ctr_sparse_sgd (dim <= 1024), or NULL: then only
+ *         row_grads is written (and required).
+ *   rounding, seed: as in ctr_sparse_sgd.
+ *   row_grads: fp32 [nnz, dim] or NULL (the gradients are not kept).
+ * Workspace: two-call query, the same size as ctr_embbag_bwd's.
  */
-int32_t ctr_embbag_bwd_sgd(const float* grad, int64_t grad_stride_b, int64_t grad_stride_t,
-                           const int64_t* offsets, int64_t batch, int32_t num_tables,
-                           int64_t nnz, const int32_t* sorted_src, const int32_t* num_unique,
-                           void* table, int32_t dtype, int64_t total_rows, int32_t dim,
-                           const int64_t* uniq, float lr, float* row_grads, void* workspace,
+int32_t ctr_embbag_bwd_sgd(const void* grad, int32_t grad_dtype, int64_t grad_stride_b,
+                           int64_t grad_stride_t, const int64_t* offsets, int64_t batch,
+                           int32_t num_tables, int64_t nnz, const int32_t* sorted_src,
+                           const int32_t* num_unique, void* table, int32_t dtype,
+                           int64_t total_rows, int32_t dim, const int64_t* uniq, float lr,
+                           int32_t rounding, uint64_t seed, float* row_grads, void* workspace,
                            size_t* workspace_bytes, void* stream);
 
 /*
- * ctr_embbag_bwd_sgd_sr -- ctr_embbag_bwd_sgd for a CTR_BF16 table with stochastic rounding
- * of the updated values (see ctr_sparse_sgd_sr for the rounding and its random bits);
- * `seed` selects the random bits of this update.  Bit-identical to ctr_embbag_bwd followed
- * by ctr_sparse_sgd_sr with the same seed.  A CTR_F32 table gives CTR_ERR_UNSUPPORTED.
- */
-int32_t ctr_embbag_bwd_sgd_sr(const float* grad, int64_t grad_stride_b, int64_t grad_stride_t,
-                              const int64_t* offsets, int64_t batch, int32_t num_tables,
-                              int64_t nnz, const int32_t* sorted_src, const int32_t* num_unique,
-                              void* table, int32_t dtype, int64_t total_rows, int32_t dim,
-                              const int64_t* uniq, float lr, uint64_t seed, float* row_grads,
-                              void* workspace, size_t* workspace_bytes, void* stream);
-
-/*
- * ctr_embbag_bwd_sgd_noalloc -- ctr_embbag_bwd_sgd_ex without a workspace, for callers that
+ * ctr_embbag_bwd_sgd_noalloc -- ctr_embbag_bwd_sgd without a workspace, for callers that
  * cannot allocate device memory (code under HIP graph capture, tight serving loops,
  * harnesses that forbid hipMalloc).  Same arguments, kernels and results (bit for bit) as
- * ctr_embbag_bwd_sgd_ex; sorted_src is required.  The reduce-by-key carries and the
- * finisher's ticket live in a device array of ctr_noalloc_scratch_capacity() bytes (64 MiB)
- * that the library holds on each GPU it runs on until the process ends, found once per device
- * on the first call there; the call allocates and frees nothing.  A batch whose carries need
- * more (ctr_embbag_bwd_noalloc_scratch_bytes(nnz, dim) above the capacity) returns
+ * ctr_embbag_bwd_sgd; sorted_src is required.  The reduce-by-key carries and the finisher's
+ * ticket live in a device array of ctr_noalloc_scratch_capacity() bytes (64 MiB) that the
+ * library holds on each GPU it runs on until the process ends, found once per device on the
+ * first call there; the call allocates and frees nothing.  A batch whose carries need more
+ * (ctr_embbag_bwd_noalloc_scratch_bytes(nnz, dim) above the capacity) returns
  * CTR_ERR_UNSUPPORTED before any launch: e.g. dim 128 with bf16 gradients holds about 3e6
  * occurrences.  Every call on a GPU shares that GPU's array, so calls that overlap on one GPU
  * (two streams, two threads) race: serialise them.
@@ -211,52 +204,33 @@ int32_t ctr_embbag_bwd_sgd_noalloc(const void* grad, int32_t grad_dtype, int64_t
 size_t ctr_embbag_bwd_noalloc_scratch_bytes(int64_t nnz, int32_t dim);
 size_t ctr_noalloc_scratch_capacity(void);
 
-/*
- * ctr_embbag_bwd_sgd_ex -- the backward of the pooling from sorted_src, in general form:
- *   grad: grad_dtype elements, CTR_F32 or CTR_BF16 (widened exactly; sums stay fp32),
- *         8-byte aligned for bf16, 16-byte for fp32;
- *   table: the SGD target as in ctr_embbag_bwd_sgd, or NULL (then only row_grads, which is
- *         required, is written);
- *   rounding: CTR_ROUND_NEAREST, or CTR_ROUND_STOCHASTIC with `seed` (bf16 table; see
- *         ctr_sparse_sgd_sr).
- * ctr_embbag_bwd_sgd and ctr_embbag_bwd_sgd_sr are this call with fp32 gradients.
- */
-int32_t ctr_embbag_bwd_sgd_ex(const void* grad, int32_t grad_dtype, int64_t grad_stride_b,
-                              int64_t grad_stride_t, const int64_t* offsets, int64_t batch,
-                              int32_t num_tables, int64_t nnz, const int32_t* sorted_src,
-                              const int32_t* num_unique, void* table, int32_t dtype,
-                              int64_t total_rows, int32_t dim, const int64_t* uniq, float lr,
-                              int32_t rounding, uint64_t seed, float* row_grads, void* workspace,
-                              size_t* workspace_bytes, void* stream);
+/* Rounding of an SGD store into a bf16 table. */
+enum { CTR_ROUND_NEAREST = 0, CTR_ROUND_STOCHASTIC = 1 };
 
 /*
  * ctr_sparse_sgd -- update of the touched rows only ([TN] "Synchronous Architecture"):
  *   table[uniq[u], :] = round(table[uniq[u], :] - lr * row_grads[u, :])
- * for u < min(num_unique[0], capacity), computed in fp32 (one fused multiply-add) and
- * stored as fp32 or rounded to bf16 nearest-even.  Keys must be distinct (ctr_unique_ids
- * output), so no two threads touch one row; untouched rows stay bit-identical.
+ * for u < min(num_unique[0], capacity).  Keys must be distinct (ctr_unique_ids output), so
+ * no two threads touch one row; untouched rows stay bit-identical.  Element (key, c),
+ * key = uniq[u]: x = fmaf(-lr, row_grads[u, c], table[key, c]) (binary32, rounded once),
+ * then stored by `rounding`:
+ *   CTR_ROUND_NEAREST     x itself (fp32 table), or x rounded to bf16 nearest-even; `seed`
+ *                         is ignored.
+ *   CTR_ROUND_STOCHASTIC  bf16 table only ("DHEN" notes, 6.4 "Common Optimizations":
+ *                         low-precision embeddings updated with stochastic rounding):
+ *       r = bits 16e .. 16e+15 (e = c mod 4) of splitmix64 from state
+ *           seed ^ (key * dim + c - e)          (one generator output per 4 columns)
+ *       stored = lo + sign(x) * ulp   if r < the low 16 bits of x's binary32 pattern
+ *                lo                   otherwise
+ *     where lo is x truncated toward zero to bf16: round away from zero with probability
+ *     (|x| - |lo|) / ulp, so the stored value is x in expectation over r.  Exact values and
+ *     infinities are kept, NaN stays NaN.  Use a fresh seed per update (ctr_sr_step_seed).
+ *     A CTR_F32 table gives CTR_ERR_UNSUPPORTED.
  */
 int32_t ctr_sparse_sgd(void* table, int32_t dtype, int64_t total_rows, int32_t dim,
                        const int64_t* uniq, const int32_t* num_unique, int64_t capacity,
-                       const float* row_grads, float lr, void* stream);
-
-/*
- * ctr_sparse_sgd_sr -- ctr_sparse_sgd for a CTR_BF16 table, with stochastic rounding
- * ("DHEN" notes, 6.4 "Common Optimizations": low-precision embeddings updated with
- * stochastic rounding).  Element (key, c), key = uniq[u]:
- *   x = fmaf(-lr, row_grads[u, c], table[key, c])            (binary32, rounded once)
- *   r = bits 16e .. 16e+15 (e = c mod 4) of splitmix64 from state
- *       seed ^ (key * dim + c - e)          (one generator output per 4 columns)
- *   stored = lo + sign(x) * ulp   if r < the low 16 bits of x's binary32 pattern
- *            lo                   otherwise
- * where lo is x truncated toward zero to bf16: round away from zero with probability
- * (|x| - |lo|) / ulp, so the stored value is x in expectation over r.  Exact values and
- * infinities are kept, NaN stays NaN.  Use a fresh seed per update (ctr_sr_step_seed).
- * A CTR_F32 table gives CTR_ERR_UNSUPPORTED.
- */
-int32_t ctr_sparse_sgd_sr(void* table, int32_t dtype, int64_t total_rows, int32_t dim,
-                          const int64_t* uniq, const int32_t* num_unique, int64_t capacity,
-                          const float* row_grads, float lr, uint64_t seed, void* stream);
+                       const float* row_grads, float lr, int32_t rounding, uint64_t seed,
+                       void* stream);
 
 /* ctr_sr_step_seed -- the seed of the k-th stochastically rounded update (k >= 0) of a run
  * seeded with `base`: output k of the splitmix64 stream whose state starts at base, i.e. the
@@ -302,23 +276,14 @@ int32_t ctr_embbag_interaction_fwd(const void* table, int32_t dtype, int64_t tot
  * i*(i-1)/2 + j] for i > j:
  *   dZ[b, i, :] = sum over j != i of dP_(max(i,j), min(i,j)) * Z[b, j, :]
  *                 + (i == 0 ? dR[b*dr_stride + 0 .. dim) : 0)
- * dZ: fp32 [batch, F, dim].  compute as in the forward (bf16 rounds dP and Z).
+ * dZ: [batch, F, dim] of dz_dtype: CTR_F32, or CTR_BF16 (nearest-even of the fp32 result;
+ * needs compute = CTR_BF16).  A bf16 dZ halves the bytes the backward of the pooling re-reads
+ * per occurrence; its consumer accumulates in fp32 (ctr_embbag_bwd_sgd with grad_dtype =
+ * CTR_BF16).  compute as in the forward (bf16 rounds dP and Z).
  */
 int32_t ctr_dot_interaction_bwd(const float* Z, const float* dR, int64_t dr_stride,
                                 int64_t batch, int32_t num_vectors, int32_t dim,
-                                int32_t compute, float* dZ, void* stream);
-
-/*
- * ctr_dot_interaction_bwd_ex -- ctr_dot_interaction_bwd (with_self = 0) or
- * ctr_dot_interaction_self_bwd (with_self != 0), with dZ stored as dz_dtype: CTR_F32, or
- * CTR_BF16 (nearest-even of the fp32 result; needs compute = CTR_BF16).  A bf16 dZ halves
- * the bytes the backward of the pooling re-reads per occurrence; its consumer accumulates in
- * fp32 (ctr_embbag_bwd_sgd_ex with grad_dtype = CTR_BF16).
- */
-int32_t ctr_dot_interaction_bwd_ex(const float* Z, const float* dR, int64_t dr_stride,
-                                   int64_t batch, int32_t num_vectors, int32_t dim,
-                                   int32_t compute, int32_t with_self, int32_t dz_dtype,
-                                   void* dZ, void* stream);
+                                int32_t compute, int32_t dz_dtype, void* dZ, void* stream);
 
 /*
  * ctr_dot_interaction_self_fwd / _self_bwd -- the pair set with self-dots, [DHEN] 3.1 ("all
@@ -327,14 +292,14 @@ int32_t ctr_dot_interaction_bwd_ex(const float* Z, const float* dR, int64_t dr_s
  *   R[b*r_stride + dim + i*(i+1)/2 + j]   = <Z[b, i, :], Z[b, j, :]>        i >= j
  *   dZ[b, i, :] = sum over j != i of dP_(max,min) Z[b, j, :] + 2 dP_ii Z[b, i, :]
  *                 + (i == 0 ? dR[b*dr_stride + 0 .. dim) : 0)
- * Same arithmetic paths, limits and errors as the strict entry points; F >= 1.
+ * Same arithmetic paths, dz_dtype, limits and errors as the strict entry points; F >= 1.
  */
 int32_t ctr_dot_interaction_self_fwd(const float* Z, int64_t batch, int32_t num_vectors,
                                      int32_t dim, int32_t compute, float* R, int64_t r_stride,
                                      void* stream);
 int32_t ctr_dot_interaction_self_bwd(const float* Z, const float* dR, int64_t dr_stride,
                                      int64_t batch, int32_t num_vectors, int32_t dim,
-                                     int32_t compute, float* dZ, void* stream);
+                                     int32_t compute, int32_t dz_dtype, void* dZ, void* stream);
 
 /*
  * ctr_fm_interaction_fwd / _bwd -- the sum of all pair dots by the squared-norm identity,
@@ -350,15 +315,15 @@ int32_t ctr_fm_interaction_bwd(const float* Z, const float* dout, int64_t batch,
                                int32_t num_vectors, int32_t dim, float* dZ, void* stream);
 
 /*
- * ctr_init_table_hash -- fills a table with the counter-based values used by the seeded
+ * ctr_init_tables_hash -- fills a table with the counter-based values used by the seeded
  * workloads (input preparation, not part of the method): element (r, c) of table t is
  * x = fp32(2u - 1) * fp32(1/sqrt(rows_t)) with u = (splitmix64 output from state
  * seed ^ (r*dim + c)) >> 40, times 2^-24, stored as fp32 or bf16 nearest-even.
  * row_base_host: host int64 [num_tables + 1].
  */
-int32_t ctr_init_table_hash(void* table, int32_t dtype, int32_t dim,
-                            const int64_t* row_base_host, int32_t num_tables, uint64_t seed,
-                            void* stream);
+int32_t ctr_init_tables_hash(void* table, int32_t dtype, int32_t dim,
+                             const int64_t* row_base_host, int32_t num_tables, uint64_t seed,
+                             void* stream);
 
 /*
  * ---------------------------------------------------------------- exported dictionary
@@ -421,8 +386,8 @@ int32_t ctr_validate_csr(const void* indices, int32_t index_type, int64_t nnz,
  *   CTR_STEP_POOLED_INTERACTION  tables + dense vector ("Meta DLRM" 02, "DHEN" notes 2.1):
  *     ctr_unique_ids over (indices, offsets, row_base) -> ctr_embbag_fwd into Z[:, 1:, :]
  *     -> ctr_dot_interaction_fwd (Z -> R) -> ctr_dot_interaction_bwd (dR -> dZ)
- *     -> ctr_embbag_bwd_sgd over dZ[:, 1:, :] (SGD on the touched rows; with
- *     rounding == CTR_ROUND_STOCHASTIC, ctr_embbag_bwd_sgd_sr, in both kinds).
+ *     -> ctr_embbag_bwd_sgd over dZ[:, 1:, :] (SGD on the touched rows, rounded by the
+ *     descriptor's rounding and seed, in both kinds).
  *     Z, dZ: fp32 [batch, num_tables + 1, dim], Z[:, 0, :] = the dense vector (input);
  *     R, dR: fp32 [batch, dim + P], P = (num_tables + 1) * num_tables / 2.
  *   CTR_STEP_BATCH_MATRIX  one table, IDs mapped by key_modulus ([TN] "Core Optimizations"):
@@ -440,7 +405,6 @@ int32_t ctr_validate_csr(const void* indices, int32_t index_type, int64_t nnz,
  */
 enum { CTR_STEP_POOLED_INTERACTION = 0, CTR_STEP_BATCH_MATRIX = 1 };
 #define CTR_STEP_SETS 3
-enum { CTR_ROUND_NEAREST = 0, CTR_ROUND_STOCHASTIC = 1 };
 enum {
   CTR_SCHEDULE_SERIAL = 0,
   CTR_SCHEDULE_PIPELINED = 1,

@@ -93,7 +93,7 @@ const char* ctr_status_string(int32_t status) {
   }
 }
 
-const char* ctr_last_error(void) { return g_msg; }
+const char* ctr_last_error_message(void) { return g_msg; }
 
 int32_t ctr_unique_ids(const void* ids, int32_t id_type, int64_t n, const int64_t* offsets,
                        int64_t batch, int32_t num_tables, const int64_t* row_base,
@@ -328,10 +328,35 @@ static int32_t embbag_bwd_sgd_common(const void* grad, bool grad_bf16, int64_t g
                     name);
 }
 
+// The dtype and rounding codes of the public entry points, checked once for all of them.
+static int32_t embbag_bwd_sgd_coded(const void* grad, int32_t grad_dtype, int64_t grad_stride_b,
+                                    int64_t grad_stride_t, const int64_t* offsets, int64_t batch,
+                                    int32_t num_tables, int64_t nnz, const int32_t* sorted_src,
+                                    const int32_t* num_unique, void* table, int32_t dtype,
+                                    int64_t total_rows, int32_t dim, const int64_t* uniq,
+                                    float lr, int32_t rounding, uint64_t seed, float* row_grads,
+                                    void* workspace, size_t* workspace_bytes, void* stream,
+                                    const char* name, void* l0_begin, void* l0_end,
+                                    bool noalloc) {
+  if (grad_dtype != CTR_F32 && grad_dtype != CTR_BF16) {
+    g_msg[0] = 0;
+    return fail(CTR_ERR_INVALID_ARGUMENT, "grad_dtype %d is not CTR_F32 or CTR_BF16", grad_dtype);
+  }
+  if (rounding != CTR_ROUND_NEAREST && rounding != CTR_ROUND_STOCHASTIC) {
+    g_msg[0] = 0;
+    return fail(CTR_ERR_INVALID_ARGUMENT, "unknown rounding %d", rounding);
+  }
+  return embbag_bwd_sgd_common(grad, grad_dtype == CTR_BF16, grad_stride_b, grad_stride_t,
+                               offsets, batch, num_tables, nnz, sorted_src, num_unique, table,
+                               dtype, total_rows, dim, uniq, lr, row_grads, workspace,
+                               workspace_bytes, rounding == CTR_ROUND_STOCHASTIC, seed, stream,
+                               name, l0_begin, l0_end, noalloc);
+}
+
 }  // extern "C"
 
 namespace ctr {
-// ctr_embbag_bwd_sgd_ex with timing marks recorded right before and after the first
+// ctr_embbag_bwd_sgd with timing marks recorded right before and after the first
 // reduce-by-key kernel (the native step runner's marks).
 int32_t embbag_bwd_sgd_marked(const void* grad, int32_t grad_dtype, int64_t grad_stride_b,
                               int64_t grad_stride_t, const int64_t* offsets, int64_t batch,
@@ -341,44 +366,28 @@ int32_t embbag_bwd_sgd_marked(const void* grad, int32_t grad_dtype, int64_t grad
                               int32_t rounding, uint64_t seed, float* row_grads, void* workspace,
                               size_t* workspace_bytes, void* stream, void* l0_begin,
                               void* l0_end) {
-  if (grad_dtype != CTR_F32 && grad_dtype != CTR_BF16) {
-    g_msg[0] = 0;
-    return fail(CTR_ERR_INVALID_ARGUMENT, "grad_dtype %d is not CTR_F32 or CTR_BF16", grad_dtype);
-  }
-  if (rounding != CTR_ROUND_NEAREST && rounding != CTR_ROUND_STOCHASTIC) {
-    g_msg[0] = 0;
-    return fail(CTR_ERR_INVALID_ARGUMENT, "unknown rounding %d", rounding);
-  }
-  return embbag_bwd_sgd_common(grad, grad_dtype == CTR_BF16, grad_stride_b, grad_stride_t,
-                               offsets, batch, num_tables, nnz, sorted_src, num_unique, table,
-                               dtype, total_rows, dim, uniq, lr, row_grads, workspace,
-                               workspace_bytes, rounding == CTR_ROUND_STOCHASTIC, seed, stream,
-                               "ctr_step_run (backward)", l0_begin, l0_end);
+  return embbag_bwd_sgd_coded(grad, grad_dtype, grad_stride_b, grad_stride_t, offsets, batch,
+                              num_tables, nnz, sorted_src, num_unique, table, dtype, total_rows,
+                              dim, uniq, lr, rounding, seed, row_grads, workspace,
+                              workspace_bytes, stream, "ctr_step_run (backward)", l0_begin,
+                              l0_end, false);
 }
 }  // namespace ctr
 
 extern "C" {
 
-int32_t ctr_embbag_bwd_sgd_ex(const void* grad, int32_t grad_dtype, int64_t grad_stride_b,
-                              int64_t grad_stride_t, const int64_t* offsets, int64_t batch,
-                              int32_t num_tables, int64_t nnz, const int32_t* sorted_src,
-                              const int32_t* num_unique, void* table, int32_t dtype,
-                              int64_t total_rows, int32_t dim, const int64_t* uniq, float lr,
-                              int32_t rounding, uint64_t seed, float* row_grads, void* workspace,
-                              size_t* workspace_bytes, void* stream) {
-  if (grad_dtype != CTR_F32 && grad_dtype != CTR_BF16) {
-    g_msg[0] = 0;
-    return fail(CTR_ERR_INVALID_ARGUMENT, "grad_dtype %d is not CTR_F32 or CTR_BF16", grad_dtype);
-  }
-  if (rounding != CTR_ROUND_NEAREST && rounding != CTR_ROUND_STOCHASTIC) {
-    g_msg[0] = 0;
-    return fail(CTR_ERR_INVALID_ARGUMENT, "unknown rounding %d", rounding);
-  }
-  return embbag_bwd_sgd_common(grad, grad_dtype == CTR_BF16, grad_stride_b, grad_stride_t,
-                               offsets, batch, num_tables, nnz, sorted_src, num_unique, table,
-                               dtype, total_rows, dim, uniq, lr, row_grads, workspace,
-                               workspace_bytes, rounding == CTR_ROUND_STOCHASTIC, seed, stream,
-                               "ctr_embbag_bwd_sgd_ex");
+int32_t ctr_embbag_bwd_sgd(const void* grad, int32_t grad_dtype, int64_t grad_stride_b,
+                           int64_t grad_stride_t, const int64_t* offsets, int64_t batch,
+                           int32_t num_tables, int64_t nnz, const int32_t* sorted_src,
+                           const int32_t* num_unique, void* table, int32_t dtype,
+                           int64_t total_rows, int32_t dim, const int64_t* uniq, float lr,
+                           int32_t rounding, uint64_t seed, float* row_grads, void* workspace,
+                           size_t* workspace_bytes, void* stream) {
+  return embbag_bwd_sgd_coded(grad, grad_dtype, grad_stride_b, grad_stride_t, offsets, batch,
+                              num_tables, nnz, sorted_src, num_unique, table, dtype, total_rows,
+                              dim, uniq, lr, rounding, seed, row_grads, workspace,
+                              workspace_bytes, stream, "ctr_embbag_bwd_sgd", nullptr, nullptr,
+                              false);
 }
 
 int32_t ctr_embbag_bwd_sgd_noalloc(const void* grad, int32_t grad_dtype, int64_t grad_stride_b,
@@ -388,19 +397,10 @@ int32_t ctr_embbag_bwd_sgd_noalloc(const void* grad, int32_t grad_dtype, int64_t
                                    int64_t total_rows, int32_t dim, const int64_t* uniq, float lr,
                                    int32_t rounding, uint64_t seed, float* row_grads,
                                    void* stream) {
-  if (grad_dtype != CTR_F32 && grad_dtype != CTR_BF16) {
-    g_msg[0] = 0;
-    return fail(CTR_ERR_INVALID_ARGUMENT, "grad_dtype %d is not CTR_F32 or CTR_BF16", grad_dtype);
-  }
-  if (rounding != CTR_ROUND_NEAREST && rounding != CTR_ROUND_STOCHASTIC) {
-    g_msg[0] = 0;
-    return fail(CTR_ERR_INVALID_ARGUMENT, "unknown rounding %d", rounding);
-  }
-  return embbag_bwd_sgd_common(grad, grad_dtype == CTR_BF16, grad_stride_b, grad_stride_t,
-                               offsets, batch, num_tables, nnz, sorted_src, num_unique, table,
-                               dtype, total_rows, dim, uniq, lr, row_grads, nullptr, nullptr,
-                               rounding == CTR_ROUND_STOCHASTIC, seed, stream,
-                               "ctr_embbag_bwd_sgd_noalloc", nullptr, nullptr, true);
+  return embbag_bwd_sgd_coded(grad, grad_dtype, grad_stride_b, grad_stride_t, offsets, batch,
+                              num_tables, nnz, sorted_src, num_unique, table, dtype, total_rows,
+                              dim, uniq, lr, rounding, seed, row_grads, nullptr, nullptr, stream,
+                              "ctr_embbag_bwd_sgd_noalloc", nullptr, nullptr, true);
 }
 
 size_t ctr_embbag_bwd_noalloc_scratch_bytes(int64_t nnz, int32_t dim) {
@@ -409,38 +409,6 @@ size_t ctr_embbag_bwd_noalloc_scratch_bytes(int64_t nnz, int32_t dim) {
 }
 
 size_t ctr_noalloc_scratch_capacity(void) { return ctr::kNoallocScratchBytes; }
-
-int32_t ctr_embbag_bwd_sgd(const float* grad, int64_t grad_stride_b, int64_t grad_stride_t,
-                           const int64_t* offsets, int64_t batch, int32_t num_tables,
-                           int64_t nnz, const int32_t* sorted_src, const int32_t* num_unique,
-                           void* table, int32_t dtype, int64_t total_rows, int32_t dim,
-                           const int64_t* uniq, float lr, float* row_grads, void* workspace,
-                           size_t* workspace_bytes, void* stream) {
-  if (!table) {
-    g_msg[0] = 0;
-    return fail(CTR_ERR_INVALID_ARGUMENT, "table is NULL");
-  }
-  return embbag_bwd_sgd_common(grad, false, grad_stride_b, grad_stride_t, offsets, batch,
-                               num_tables, nnz, sorted_src, num_unique, table, dtype, total_rows,
-                               dim, uniq, lr, row_grads, workspace, workspace_bytes, false, 0,
-                               stream, "ctr_embbag_bwd_sgd");
-}
-
-int32_t ctr_embbag_bwd_sgd_sr(const float* grad, int64_t grad_stride_b, int64_t grad_stride_t,
-                              const int64_t* offsets, int64_t batch, int32_t num_tables,
-                              int64_t nnz, const int32_t* sorted_src, const int32_t* num_unique,
-                              void* table, int32_t dtype, int64_t total_rows, int32_t dim,
-                              const int64_t* uniq, float lr, uint64_t seed, float* row_grads,
-                              void* workspace, size_t* workspace_bytes, void* stream) {
-  if (!table) {
-    g_msg[0] = 0;
-    return fail(CTR_ERR_INVALID_ARGUMENT, "table is NULL");
-  }
-  return embbag_bwd_sgd_common(grad, false, grad_stride_b, grad_stride_t, offsets, batch,
-                               num_tables, nnz, sorted_src, num_unique, table, dtype, total_rows,
-                               dim, uniq, lr, row_grads, workspace, workspace_bytes, true, seed,
-                               stream, "ctr_embbag_bwd_sgd_sr");
-}
 
 static int32_t sparse_sgd_common(void* table, int32_t dtype, int64_t total_rows, int32_t dim,
                                  const int64_t* uniq, const int32_t* num_unique,
@@ -465,9 +433,14 @@ static int32_t sparse_sgd_common(void* table, int32_t dtype, int64_t total_rows,
 
 int32_t ctr_sparse_sgd(void* table, int32_t dtype, int64_t total_rows, int32_t dim,
                        const int64_t* uniq, const int32_t* num_unique, int64_t capacity,
-                       const float* row_grads, float lr, void* stream) {
+                       const float* row_grads, float lr, int32_t rounding, uint64_t seed,
+                       void* stream) {
+  if (rounding != CTR_ROUND_NEAREST && rounding != CTR_ROUND_STOCHASTIC) {
+    g_msg[0] = 0;
+    return fail(CTR_ERR_INVALID_ARGUMENT, "unknown rounding %d", rounding);
+  }
   return sparse_sgd_common(table, dtype, total_rows, dim, uniq, num_unique, capacity, row_grads,
-                           lr, false, 0, stream, "ctr_sparse_sgd");
+                           lr, rounding == CTR_ROUND_STOCHASTIC, seed, stream, "ctr_sparse_sgd");
 }
 
 uint64_t ctr_sr_step_seed(uint64_t base, int64_t k) {
@@ -475,13 +448,6 @@ uint64_t ctr_sr_step_seed(uint64_t base, int64_t k) {
   z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
   z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
   return z ^ (z >> 31);
-}
-
-int32_t ctr_sparse_sgd_sr(void* table, int32_t dtype, int64_t total_rows, int32_t dim,
-                          const int64_t* uniq, const int32_t* num_unique, int64_t capacity,
-                          const float* row_grads, float lr, uint64_t seed, void* stream) {
-  return sparse_sgd_common(table, dtype, total_rows, dim, uniq, num_unique, capacity, row_grads,
-                           lr, true, seed, stream, "ctr_sparse_sgd_sr");
 }
 
 static int32_t check_interaction(const float* Z, int64_t batch, int32_t F, int32_t dim,
@@ -518,9 +484,12 @@ static int32_t interaction_fwd_common(const float* Z, int64_t batch, int32_t F, 
 
 static int32_t interaction_bwd_common(const float* Z, const float* dR, int64_t dr_stride,
                                       int64_t batch, int32_t F, int32_t dim, int32_t compute,
-                                      bool self, bool dz_bf16, void* dZ, void* stream,
+                                      bool self, int32_t dz_dtype, void* dZ, void* stream,
                                       const char* name) {
   g_msg[0] = 0;
+  if (dz_dtype != CTR_F32 && dz_dtype != CTR_BF16)
+    return fail(CTR_ERR_INVALID_ARGUMENT, "dz_dtype %d is not CTR_F32 or CTR_BF16", dz_dtype);
+  const bool dz_bf16 = dz_dtype == CTR_BF16;
   int32_t st = check_interaction(Z, batch, F, dim, compute, self, static_cast<const float*>(dZ),
                                  dr_stride);
   if (st) return st;
@@ -531,19 +500,6 @@ static int32_t interaction_bwd_common(const float* Z, const float* dR, int64_t d
                                                 compute == CTR_BF16, self, dz_bf16, dZ,
                                                 (hipStream_t)stream),
                     name);
-}
-
-int32_t ctr_dot_interaction_bwd_ex(const float* Z, const float* dR, int64_t dr_stride,
-                                   int64_t batch, int32_t num_vectors, int32_t dim,
-                                   int32_t compute, int32_t with_self, int32_t dz_dtype,
-                                   void* dZ, void* stream) {
-  if (dz_dtype != CTR_F32 && dz_dtype != CTR_BF16) {
-    g_msg[0] = 0;
-    return fail(CTR_ERR_INVALID_ARGUMENT, "dz_dtype %d is not CTR_F32 or CTR_BF16", dz_dtype);
-  }
-  return interaction_bwd_common(Z, dR, dr_stride, batch, num_vectors, dim, compute,
-                                with_self != 0, dz_dtype == CTR_BF16, dZ, stream,
-                                "ctr_dot_interaction_bwd_ex");
 }
 
 int32_t ctr_dot_interaction_fwd(const float* Z, int64_t batch, int32_t num_vectors, int32_t dim,
@@ -590,9 +546,9 @@ int32_t ctr_embbag_interaction_fwd(const void* table, int32_t dtype, int64_t tot
 
 int32_t ctr_dot_interaction_bwd(const float* Z, const float* dR, int64_t dr_stride,
                                 int64_t batch, int32_t num_vectors, int32_t dim, int32_t compute,
-                                float* dZ, void* stream) {
-  return interaction_bwd_common(Z, dR, dr_stride, batch, num_vectors, dim, compute, false, false,
-                                dZ, stream, "ctr_dot_interaction_bwd");
+                                int32_t dz_dtype, void* dZ, void* stream) {
+  return interaction_bwd_common(Z, dR, dr_stride, batch, num_vectors, dim, compute, false,
+                                dz_dtype, dZ, stream, "ctr_dot_interaction_bwd");
 }
 
 int32_t ctr_dot_interaction_self_fwd(const float* Z, int64_t batch, int32_t num_vectors,
@@ -604,9 +560,9 @@ int32_t ctr_dot_interaction_self_fwd(const float* Z, int64_t batch, int32_t num_
 
 int32_t ctr_dot_interaction_self_bwd(const float* Z, const float* dR, int64_t dr_stride,
                                      int64_t batch, int32_t num_vectors, int32_t dim,
-                                     int32_t compute, float* dZ, void* stream) {
-  return interaction_bwd_common(Z, dR, dr_stride, batch, num_vectors, dim, compute, true, false,
-                                dZ, stream, "ctr_dot_interaction_self_bwd");
+                                     int32_t compute, int32_t dz_dtype, void* dZ, void* stream) {
+  return interaction_bwd_common(Z, dR, dr_stride, batch, num_vectors, dim, compute, true,
+                                dz_dtype, dZ, stream, "ctr_dot_interaction_self_bwd");
 }
 
 static int32_t check_fm(const float* Z, int64_t batch, int32_t F, int32_t dim, const float* a,
@@ -701,7 +657,7 @@ int32_t ctr_dict_embbag_fwd(const int64_t* values, int64_t nnz, const int64_t* o
                     "ctr_dict_embbag_fwd");
 }
 
-int32_t ctr_init_table_hash(void* table, int32_t dtype, int32_t dim, const int64_t* row_base_host,
+int32_t ctr_init_tables_hash(void* table, int32_t dtype, int32_t dim, const int64_t* row_base_host,
                             int32_t num_tables, uint64_t seed, void* stream) {
   g_msg[0] = 0;
   if (!row_base_host || num_tables < 1)
@@ -717,7 +673,7 @@ int32_t ctr_init_table_hash(void* table, int32_t dtype, int32_t dim, const int64
     const float scale = (float)(1.0 / std::sqrt((double)rows));
     hipError_t e = ctr::launch_init_table(table, dtype == CTR_BF16, dim, row_base_host[t], rows,
                                           scale, seed, (hipStream_t)stream);
-    if (e != hipSuccess) return hip_status(e, "ctr_init_table_hash");
+    if (e != hipSuccess) return hip_status(e, "ctr_init_tables_hash");
   }
   return CTR_OK;
 }

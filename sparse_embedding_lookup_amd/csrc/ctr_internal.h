@@ -107,7 +107,7 @@ inline RowGeom row_geom(int64_t vecs) {
   return {G, VPL};
 }
 
-// Records the thread's ctr_last_error text and returns code (capi.cpp).
+// Records the thread's ctr_last_error_message text and returns code (capi.cpp).
 int32_t set_error(int32_t code, const char* msg);
 
 // Records timing event `ev` (nothing when NULL) on stream s.  Under stream capture it adds an

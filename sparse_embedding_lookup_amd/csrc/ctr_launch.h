@@ -61,7 +61,7 @@ hipError_t launch_embbag_bwd_noalloc(const void* grad, bool grad_bf16, int64_t s
                                      float* row_grads, void* table, int sgd_mode,
                                      int64_t total_rows, const int64_t* uniq, float lr,
                                      uint64_t seed, hipStream_t s);
-// The fused backward + SGD entry (ctr_embbag_bwd_sgd_ex) with timing marks around its first
+// The fused backward + SGD entry (ctr_embbag_bwd_sgd) with timing marks around its first
 // reduce-by-key kernel (capi.cpp).
 int32_t embbag_bwd_sgd_marked(const void* grad, int32_t grad_dtype, int64_t grad_stride_b,
                               int64_t grad_stride_t, const int64_t* offsets, int64_t batch,

@@ -83,8 +83,8 @@ int32_t interaction_part(const ctr_step_t* d, hipStream_t s) {
   const int64_t F = (int64_t)d->num_tables + 1;
   CTR_TRY(ctr_dot_interaction_fwd(d->Z, d->batch, (int32_t)F, d->dim, d->compute, d->R,
                                   d->dim + F * (F - 1) / 2, s));
-  return ctr_dot_interaction_bwd_ex(d->Z, d->dR, d->dim + F * (F - 1) / 2, d->batch,
-                                    (int32_t)F, d->dim, d->compute, 0, d->grad_dtype, d->dZ, s);
+  return ctr_dot_interaction_bwd(d->Z, d->dR, d->dim + F * (F - 1) / 2, d->batch, (int32_t)F,
+                                 d->dim, d->compute, d->grad_dtype, d->dZ, s);
 }
 
 // The backward with the SGD update of the touched rows; with mark_stage CTR_MARK_BACKWARD the

@@ -22,14 +22,15 @@ CTR_F32, CTR_BF16 = 0, 1
 CTR_I32, CTR_I64 = 0, 1
 
 EXPORTED = [
-    "ctr_version", "ctr_status_string", "ctr_last_error", "ctr_unique_ids", "ctr_gather_rows",
+    "ctr_version", "ctr_status_string", "ctr_last_error_message", "ctr_unique_ids",
+    "ctr_gather_rows",
     "ctr_embbag_fwd", "ctr_embbag_bwd", "ctr_embbag_bwd_sgd", "ctr_sparse_sgd",
     "ctr_dot_interaction_fwd",
-    "ctr_dot_interaction_bwd", "ctr_init_table_hash", "ctr_validate_csr", "ctr_step_run",
-    "ctr_step_unique", "ctr_embbag_bwd_sgd_sr", "ctr_sparse_sgd_sr", "ctr_sr_step_seed",
+    "ctr_dot_interaction_bwd", "ctr_init_tables_hash", "ctr_validate_csr", "ctr_step_run",
+    "ctr_step_unique", "ctr_sr_step_seed",
     "ctr_dot_interaction_self_fwd", "ctr_dot_interaction_self_bwd", "ctr_fm_interaction_fwd",
     "ctr_fm_interaction_bwd", "ctr_dict_build", "ctr_dict_lookup", "ctr_dict_embbag_fwd",
-    "ctr_dot_interaction_bwd_ex", "ctr_embbag_bwd_sgd_ex", "ctr_step_run_deep",
+    "ctr_step_run_deep",
     "ctr_dense_fwd", "ctr_dense_bwd_sgd", "ctr_logistic_ne", "ctr_embbag_interaction_fwd",
     "ctr_embbag_bwd_sgd_noalloc", "ctr_embbag_bwd_noalloc_scratch_bytes",
     "ctr_noalloc_scratch_capacity",
@@ -88,26 +89,20 @@ def load() -> ctypes.CDLL:
     sig = {
         "ctr_version": (i32, []),
         "ctr_status_string": (ctypes.c_char_p, [i32]),
-        "ctr_last_error": (ctypes.c_char_p, []),
+        "ctr_last_error_message": (ctypes.c_char_p, []),
         "ctr_unique_ids": (i32, [P, i32, i64, P, i64, i32, P, i64, i64, i64, P, P, P, P, P, P, P,
                                  PS, P]),
         "ctr_gather_rows": (i32, [P, i32, i64, i32, P, P, i64, P, P]),
         "ctr_embbag_fwd": (i32, [P, i32, i64, i32, P, i32, P, i32, i64, P, i64, P, i64, i64, P]),
         "ctr_embbag_bwd": (i32, [P, i64, i64, P, i64, i32, i32, i64, P, P, P, P, P, P, PS, P]),
-        "ctr_embbag_bwd_sgd": (i32, [P, i64, i64, P, i64, i32, i64, P, P, P, i32, i64, i32, P,
-                                     f32, P, P, PS, P]),
-        "ctr_sparse_sgd": (i32, [P, i32, i64, i32, P, P, i64, P, f32, P]),
-        "ctr_embbag_bwd_sgd_sr": (i32, [P, i64, i64, P, i64, i32, i64, P, P, P, i32, i64, i32,
-                                        P, f32, u64, P, P, PS, P]),
-        "ctr_sparse_sgd_sr": (i32, [P, i32, i64, i32, P, P, i64, P, f32, u64, P]),
+        "ctr_embbag_bwd_sgd": (i32, [P, i32, i64, i64, P, i64, i32, i64, P, P, P, i32, i64,
+                                     i32, P, f32, i32, u64, P, P, PS, P]),
+        "ctr_sparse_sgd": (i32, [P, i32, i64, i32, P, P, i64, P, f32, i32, u64, P]),
         "ctr_sr_step_seed": (u64, [u64, i64]),
         "ctr_dot_interaction_self_fwd": (i32, [P, i64, i32, i32, i32, P, i64, P]),
-        "ctr_dot_interaction_self_bwd": (i32, [P, P, i64, i64, i32, i32, i32, P, P]),
+        "ctr_dot_interaction_self_bwd": (i32, [P, P, i64, i64, i32, i32, i32, i32, P, P]),
         "ctr_fm_interaction_fwd": (i32, [P, i64, i32, i32, P, P]),
         "ctr_fm_interaction_bwd": (i32, [P, P, i64, i32, i32, P, P]),
-        "ctr_dot_interaction_bwd_ex": (i32, [P, P, i64, i64, i32, i32, i32, i32, i32, P, P]),
-        "ctr_embbag_bwd_sgd_ex": (i32, [P, i32, i64, i64, P, i64, i32, i64, P, P, P, i32, i64,
-                                        i32, P, f32, i32, u64, P, P, PS, P]),
         "ctr_embbag_bwd_sgd_noalloc": (i32, [P, i32, i64, i64, P, i64, i32, i64, P, P, P, i32,
                                              i64, i32, P, f32, i32, u64, P, P]),
         "ctr_embbag_bwd_noalloc_scratch_bytes": (sz, [i64, i32]),
@@ -119,8 +114,8 @@ def load() -> ctypes.CDLL:
         "ctr_dot_interaction_fwd": (i32, [P, i64, i32, i32, i32, P, i64, P]),
         "ctr_embbag_interaction_fwd": (i32, [P, i32, i64, i32, P, i32, P, i32, i64, P, i64, P,
                                              i32, P, i64, P]),
-        "ctr_dot_interaction_bwd": (i32, [P, P, i64, i64, i32, i32, i32, P, P]),
-        "ctr_init_table_hash": (i32, [P, i32, i32, P, i32, u64, P]),
+        "ctr_dot_interaction_bwd": (i32, [P, P, i64, i64, i32, i32, i32, i32, P, P]),
+        "ctr_init_tables_hash": (i32, [P, i32, i32, P, i32, u64, P]),
         "ctr_validate_csr": (i32, [P, i32, i64, P, i64, i32, P, i64, P, P]),
         "ctr_step_run": (i32, [P, i64, i32, P, P, P, P, P, P]),
         "ctr_step_unique": (i32, [P, i32, P]),
@@ -149,7 +144,7 @@ def _stream(stream=None):
 
 def _check(fn: str, status: int) -> None:
     if status != CTR_OK:
-        raise CtrError(fn, status, load().ctr_last_error().decode())
+        raise CtrError(fn, status, load().ctr_last_error_message().decode())
 
 
 class Call:
@@ -293,9 +288,10 @@ def ctr_embbag_bwd(grad: torch.Tensor, grad_stride_b: int, grad_stride_t: int,
     if grad.dtype == torch.bfloat16:
         if workspace is None:
             workspace = _workspace(embbag_bwd_workspace_bytes(nnz, dim), dev)
-        return _bwd_ex(grad, grad_stride_b, grad_stride_t, offsets, batch, num_tables, nnz,
-                       sorted_src, num_unique, None, None, dim, 0.0, CTR_ROUND_NEAREST, 0,
-                       row_grads, workspace, stream, prepare)
+        return ctr_embbag_bwd_sgd(grad, grad_stride_b, grad_stride_t, offsets, batch,
+                                  num_tables, nnz, sorted_src, num_unique, None, None, 0.0,
+                                  row_grads=row_grads, workspace=workspace, dim=dim,
+                                  stream=stream, prepare=prepare)
     args = (_ptr(grad), grad_stride_b, grad_stride_t, _ptr(offsets), batch, num_tables, dim, nnz,
             _ptr(perm), _ptr(inverse), _ptr(sorted_src), _ptr(num_unique), _ptr(row_grads))
     if workspace is None:
@@ -308,59 +304,25 @@ def ctr_embbag_bwd(grad: torch.Tensor, grad_stride_b: int, grad_stride_t: int,
 
 def ctr_embbag_bwd_sgd(grad: torch.Tensor, grad_stride_b: int, grad_stride_t: int,
                        offsets: torch.Tensor, batch: int, num_tables: int, nnz: int,
-                       sorted_src: torch.Tensor, num_unique: torch.Tensor, table: torch.Tensor,
-                       uniq: torch.Tensor, lr: float, row_grads: Optional[torch.Tensor] = None,
-                       workspace: Optional[torch.Tensor] = None, stream=None,
-                       prepare: bool = False):
-    """Per-row gradient sums applied straight to the table as the sparse SGD update."""
-    total_rows, dim = table.shape
+                       sorted_src: torch.Tensor, num_unique: torch.Tensor,
+                       table: Optional[torch.Tensor], uniq: Optional[torch.Tensor], lr: float,
+                       row_grads: Optional[torch.Tensor] = None,
+                       workspace: Optional[torch.Tensor] = None,
+                       rounding: int = CTR_ROUND_NEAREST, seed: int = 0, dim: int = 0,
+                       stream=None, prepare: bool = False):
+    """Per-row gradient sums applied straight to the table as the sparse SGD update, rounded
+    by ``rounding`` (stochastic: random bits from ``seed``).  The gradient type is the
+    tensor's (fp32 or bf16); table None: row sums into row_grads only (dim then required)."""
+    total_rows, d = (0, dim) if table is None else table.shape
     if workspace is None:
-        workspace = _workspace(embbag_bwd_workspace_bytes(nnz, dim), grad.device)
-    if grad.dtype == torch.bfloat16:
-        return _bwd_ex(grad, grad_stride_b, grad_stride_t, offsets, batch, num_tables, nnz,
-                       sorted_src, num_unique, table, uniq, dim, lr, CTR_ROUND_NEAREST, 0,
-                       row_grads, workspace, stream, prepare)
+        workspace = _workspace(embbag_bwd_workspace_bytes(nnz, d), grad.device)
     wsb = ctypes.c_size_t(workspace.numel())
-    args = (_ptr(grad), grad_stride_b, grad_stride_t, _ptr(offsets), batch, num_tables, nnz,
-            _ptr(sorted_src), _ptr(num_unique), _ptr(table), _dtype_code(table), total_rows, dim,
-            _ptr(uniq), ctypes.c_float(lr), _ptr(row_grads), _ptr(workspace), ctypes.byref(wsb))
-    return _run("ctr_embbag_bwd_sgd", args, stream, prepare, row_grads)
-
-
-def ctr_embbag_bwd_sgd_sr(grad: torch.Tensor, grad_stride_b: int, grad_stride_t: int,
-                          offsets: torch.Tensor, batch: int, num_tables: int, nnz: int,
-                          sorted_src: torch.Tensor, num_unique: torch.Tensor,
-                          table: torch.Tensor, uniq: torch.Tensor, lr: float, seed: int,
-                          row_grads: Optional[torch.Tensor] = None,
-                          workspace: Optional[torch.Tensor] = None, stream=None,
-                          prepare: bool = False):
-    """ctr_embbag_bwd_sgd with stochastic rounding of a bf16 table (random bits from seed)."""
-    total_rows, dim = table.shape
-    if workspace is None:
-        workspace = _workspace(embbag_bwd_workspace_bytes(nnz, dim), grad.device)
-    if grad.dtype == torch.bfloat16:
-        return _bwd_ex(grad, grad_stride_b, grad_stride_t, offsets, batch, num_tables, nnz,
-                       sorted_src, num_unique, table, uniq, dim, lr, CTR_ROUND_STOCHASTIC, seed,
-                       row_grads, workspace, stream, prepare)
-    wsb = ctypes.c_size_t(workspace.numel())
-    args = (_ptr(grad), grad_stride_b, grad_stride_t, _ptr(offsets), batch, num_tables, nnz,
-            _ptr(sorted_src), _ptr(num_unique), _ptr(table), _dtype_code(table), total_rows, dim,
-            _ptr(uniq), ctypes.c_float(lr), ctypes.c_uint64(seed & 0xFFFFFFFFFFFFFFFF),
-            _ptr(row_grads), _ptr(workspace), ctypes.byref(wsb))
-    return _run("ctr_embbag_bwd_sgd_sr", args, stream, prepare, row_grads)
-
-
-def _bwd_ex(grad, sb, st, offsets, batch, num_tables, nnz, sorted_src, num_unique, table, uniq,
-            dim, lr, rounding, seed, row_grads, workspace, stream, prepare):
-    """ctr_embbag_bwd_sgd_ex: gradient dtype from the tensor; table None = row sums only."""
-    total_rows = 0 if table is None else table.shape[0]
-    wsb = ctypes.c_size_t(workspace.numel())
-    args = (_ptr(grad), _dtype_code(grad), sb, st, _ptr(offsets), batch, num_tables, nnz,
-            _ptr(sorted_src), _ptr(num_unique), _ptr(table),
-            CTR_F32 if table is None else _dtype_code(table), total_rows, dim, _ptr(uniq),
+    args = (_ptr(grad), _dtype_code(grad), grad_stride_b, grad_stride_t, _ptr(offsets), batch,
+            num_tables, nnz, _ptr(sorted_src), _ptr(num_unique), _ptr(table),
+            CTR_F32 if table is None else _dtype_code(table), total_rows, d, _ptr(uniq),
             ctypes.c_float(lr), rounding, ctypes.c_uint64(seed & 0xFFFFFFFFFFFFFFFF),
             _ptr(row_grads), _ptr(workspace), ctypes.byref(wsb))
-    return _run("ctr_embbag_bwd_sgd_ex", args, stream, prepare, row_grads)
+    return _run("ctr_embbag_bwd_sgd", args, stream, prepare, row_grads)
 
 
 def ctr_embbag_bwd_sgd_noalloc(grad: torch.Tensor, grad_stride_b: int, grad_stride_t: int,
@@ -370,7 +332,7 @@ def ctr_embbag_bwd_sgd_noalloc(grad: torch.Tensor, grad_stride_b: int, grad_stri
                                lr: float, row_grads: Optional[torch.Tensor] = None,
                                rounding: int = CTR_ROUND_NEAREST, seed: int = 0, dim: int = 0,
                                stream=None, prepare: bool = False):
-    """ctr_embbag_bwd_sgd_ex without a workspace: the library's per-GPU scratch holds the
+    """ctr_embbag_bwd_sgd without a workspace: the library's per-GPU scratch holds the
     reduce-by-key carries (table None: row sums into row_grads only; dim then required)."""
     total_rows, d = (0, dim) if table is None else table.shape
     args = (_ptr(grad), _dtype_code(grad), grad_stride_b, grad_stride_t, _ptr(offsets), batch,
@@ -389,28 +351,21 @@ def noalloc_scratch_capacity() -> int:
     return int(load().ctr_noalloc_scratch_capacity())
 
 
-def ctr_sparse_sgd_sr(table: torch.Tensor, uniq: torch.Tensor, num_unique: torch.Tensor,
-                      capacity: int, row_grads: torch.Tensor, lr: float, seed: int, stream=None,
-                      prepare: bool = False):
-    """ctr_sparse_sgd with stochastic rounding of a bf16 table (random bits from seed)."""
-    total_rows, dim = table.shape
-    args = (_ptr(table), _dtype_code(table), total_rows, dim, _ptr(uniq), _ptr(num_unique),
-            capacity, _ptr(row_grads), ctypes.c_float(lr),
-            ctypes.c_uint64(seed & 0xFFFFFFFFFFFFFFFF))
-    return _run("ctr_sparse_sgd_sr", args, stream, prepare)
-
-
 def ctr_sr_step_seed(base: int, k: int) -> int:
     """Seed of the k-th stochastically rounded update of a run seeded with base."""
     return int(load().ctr_sr_step_seed(base & 0xFFFFFFFFFFFFFFFF, k))
 
 
 def ctr_sparse_sgd(table: torch.Tensor, uniq: torch.Tensor, num_unique: torch.Tensor,
-                   capacity: int, row_grads: torch.Tensor, lr: float, stream=None,
+                   capacity: int, row_grads: torch.Tensor, lr: float,
+                   rounding: int = CTR_ROUND_NEAREST, seed: int = 0, stream=None,
                    prepare: bool = False):
+    """Update of the touched rows, rounded by ``rounding`` (stochastic: bf16 table, random
+    bits from ``seed``)."""
     total_rows, dim = table.shape
     args = (_ptr(table), _dtype_code(table), total_rows, dim, _ptr(uniq), _ptr(num_unique),
-            capacity, _ptr(row_grads), ctypes.c_float(lr))
+            capacity, _ptr(row_grads), ctypes.c_float(lr), rounding,
+            ctypes.c_uint64(seed & 0xFFFFFFFFFFFFFFFF))
     return _run("ctr_sparse_sgd", args, stream, prepare)
 
 
@@ -451,10 +406,7 @@ def ctr_dot_interaction_bwd(Z: torch.Tensor, dR: torch.Tensor, compute: int = CT
     B, F, d = Z.shape
     if dZ is None:
         dZ = torch.empty_like(Z)
-    if dZ.dtype == torch.bfloat16:
-        args = (_ptr(Z), _ptr(dR), dR.stride(0), B, F, d, compute, 0, CTR_BF16, _ptr(dZ))
-        return _run("ctr_dot_interaction_bwd_ex", args, stream, prepare, dZ)
-    args = (_ptr(Z), _ptr(dR), dR.stride(0), B, F, d, compute, _ptr(dZ))
+    args = (_ptr(Z), _ptr(dR), dR.stride(0), B, F, d, compute, _dtype_code(dZ), _ptr(dZ))
     return _run("ctr_dot_interaction_bwd", args, stream, prepare, dZ)
 
 
@@ -473,10 +425,11 @@ def ctr_dot_interaction_self_fwd(Z: torch.Tensor, compute: int = CTR_F32,
 def ctr_dot_interaction_self_bwd(Z: torch.Tensor, dR: torch.Tensor, compute: int = CTR_F32,
                                  dZ: Optional[torch.Tensor] = None, stream=None,
                                  prepare: bool = False):
+    """dZ fp32, or bf16 when ``dZ`` is a bf16 tensor (compute must be CTR_BF16)."""
     B, F, d = Z.shape
     if dZ is None:
         dZ = torch.empty_like(Z)
-    args = (_ptr(Z), _ptr(dR), dR.stride(0), B, F, d, compute, _ptr(dZ))
+    args = (_ptr(Z), _ptr(dR), dR.stride(0), B, F, d, compute, _dtype_code(dZ), _ptr(dZ))
     return _run("ctr_dot_interaction_self_bwd", args, stream, prepare, dZ)
 
 
@@ -572,7 +525,8 @@ def ctr_logistic_ne(logits: torch.Tensor, labels: torch.Tensor,
     return _run("ctr_logistic_ne", args, stream, prepare, stats)
 
 
-def ctr_init_table_hash(table: torch.Tensor, rows: Sequence[int], seed: int, stream=None) -> None:
+def ctr_init_tables_hash(table: torch.Tensor, rows: Sequence[int], seed: int,
+                         stream=None) -> None:
     lib = load()
     rb = (ctypes.c_int64 * (len(rows) + 1))()
     acc = 0
@@ -580,7 +534,7 @@ def ctr_init_table_hash(table: torch.Tensor, rows: Sequence[int], seed: int, str
         rb[t] = acc
         acc += int(r)
     rb[len(rows)] = acc
-    _check("ctr_init_table_hash", lib.ctr_init_table_hash(
+    _check("ctr_init_tables_hash", lib.ctr_init_tables_hash(
         _ptr(table), _dtype_code(table), table.shape[1], ctypes.cast(rb, ctypes.c_void_p),
         len(rows), ctypes.c_uint64(seed & 0xFFFFFFFFFFFFFFFF), _stream(stream)))
 

@@ -68,7 +68,7 @@ class FrontEnd:
         tdt = torch.bfloat16 if self.bf16 else torch.float32
         if table is None:
             table = torch.empty((w.total_rows, w.dim), dtype=tdt, device=self.device)
-            ctr.ctr_init_table_hash(table, w.rows, w.table_seed)
+            ctr.ctr_init_tables_hash(table, w.rows, w.table_seed)
         self.table = table
         self.row_base = _dev(w.row_base, self.device)
         self.indices = _dev(w.indices, self.device)
@@ -207,8 +207,9 @@ class FrontEnd:
 
     def _sparse_sgd(self):
         if self.rounding == "stochastic":
-            ctr.ctr_sparse_sgd_sr(self.table, self.uniq, self.num_unique, self.nnz,
-                                  self.row_grads, self.w.lr, self._sr_seed_next())
+            ctr.ctr_sparse_sgd(self.table, self.uniq, self.num_unique, self.nnz,
+                               self.row_grads, self.w.lr, ctr.CTR_ROUND_STOCHASTIC,
+                               self._sr_seed_next())
             return
         self._c_sparse_sgd()
 
@@ -225,10 +226,11 @@ class FrontEnd:
                 grad, sb, st, B, T = self.dZ[:, 1:, :], w.F * d, d, w.batch, w.num_tables
             else:
                 grad, sb, st, B, T = self.dout, d, 0, self.nnz, 1
-            ctr.ctr_embbag_bwd_sgd_sr(grad, sb, st, self.offsets, B, T, self.nnz,
-                                      self.sorted_src, self.num_unique, self.table, self.uniq,
-                                      w.lr, self._sr_seed_next(), row_grads=self.row_grads,
-                                      workspace=self.ws_bwd)
+            ctr.ctr_embbag_bwd_sgd(grad, sb, st, self.offsets, B, T, self.nnz,
+                                   self.sorted_src, self.num_unique, self.table, self.uniq,
+                                   w.lr, row_grads=self.row_grads, workspace=self.ws_bwd,
+                                   rounding=ctr.CTR_ROUND_STOCHASTIC,
+                                   seed=self._sr_seed_next())
             return
         self._c_embbag_bwd_sgd()
 

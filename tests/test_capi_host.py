@@ -69,7 +69,7 @@ def test_unique_workspace_query_and_bad_args():
     big = ctypes.c_size_t(wsb.value)
     st = lib.ctr_unique_ids(FAKE, 1, 1000, None, 0, 0, None, 0, 0, 0, FAKE, FAKE, FAKE, None, None,
                             None, MISALIGNED, ctypes.byref(big), None)
-    assert st == ctr.CTR_ERR_UNSUPPORTED and b"aligned" in lib.ctr_last_error()
+    assert st == ctr.CTR_ERR_UNSUPPORTED and b"aligned" in lib.ctr_last_error_message()
     assert lib.ctr_unique_ids(FAKE, 1, -1, None, 0, 0, None, 0, 0, 0, None, None, None, None, None,
                               None, None, ctypes.byref(wsb), None) == ctr.CTR_ERR_INVALID_ARGUMENT
     assert lib.ctr_unique_ids(FAKE, 1, 2 ** 31, None, 0, 0, None, 0, 0, 0, None, None, None, None,
@@ -79,7 +79,7 @@ def test_unique_workspace_query_and_bad_args():
     # row_base without offsets
     assert lib.ctr_unique_ids(FAKE, 1, 10, None, 4, 2, FAKE, 100, 0, 0, None, None, None, None, None,
                               None, None, ctypes.byref(wsb), None) == ctr.CTR_ERR_INVALID_ARGUMENT
-    assert b"offsets" in lib.ctr_last_error()
+    assert b"offsets" in lib.ctr_last_error_message()
     # a negative largest-table hint
     assert lib.ctr_unique_ids(FAKE, 1, 10, FAKE, 4, 2, FAKE, 100, -1, 0, None, None, None, None,
                               None, None, None, ctypes.byref(wsb), None) == \
@@ -145,7 +145,7 @@ def test_embbag_interaction_fwd_bad_args():
     assert call(c=1, T=128, rs=16 + 129 * 128 // 2) == ctr.CTR_ERR_UNSUPPORTED   # F > 128
     # an fp32 copy of one sample above 46 KiB: F = 101, d = 128 -> 52 KB
     assert call(dim=128, T=100, rs=128 + 101 * 50) == ctr.CTR_ERR_UNSUPPORTED
-    assert b"fused shape" in lib.ctr_last_error()
+    assert b"fused shape" in lib.ctr_last_error_message()
     # batch 0 is a no-op that launches nothing
     assert call(B=0, nnz=0, idx=None, off=None, Z=None, R=None) == ctr.CTR_OK
 
@@ -179,42 +179,59 @@ def test_interaction_bad_args():
     assert f(FAKE, 10, 200, 128, 1, FAKE, 30000, None) == ctr.CTR_ERR_UNSUPPORTED    # bf16 F
     assert f(MISALIGNED, 10, 5, 16, 1, FAKE, 26, None) == ctr.CTR_ERR_UNSUPPORTED
     b = lib.ctr_dot_interaction_bwd
-    assert b(FAKE, None, 26, 10, 5, 16, 0, FAKE, None) == ctr.CTR_ERR_INVALID_ARGUMENT  # dR NULL
+    assert b(FAKE, None, 26, 10, 5, 16, 0, 0, FAKE, None) == ctr.CTR_ERR_INVALID_ARGUMENT  # dR NULL
+    # dZ type: an unknown code, and bf16 storage without bf16 compute
+    assert b(FAKE, FAKE, 26, 10, 5, 16, 1, 7, FAKE, None) == ctr.CTR_ERR_INVALID_ARGUMENT
+    assert b"dz_dtype" in lib.ctr_last_error_message()
+    assert b(FAKE, FAKE, 26, 10, 5, 16, 0, 1, FAKE, None) == ctr.CTR_ERR_UNSUPPORTED
 
 
 def test_sgd_gather_init_validate_bad_args():
     lib = _lib()
+    s0 = ctypes.c_uint64(0)
     assert lib.ctr_sparse_sgd(FAKE, 0, 100, 16, FAKE, FAKE, 10, FAKE,
-                              ctypes.c_float(float("nan")), None) == ctr.CTR_ERR_INVALID_ARGUMENT
+                              ctypes.c_float(float("nan")), 0, s0, None) == \
+        ctr.CTR_ERR_INVALID_ARGUMENT
     assert lib.ctr_sparse_sgd(FAKE, 0, 100, 16, FAKE, FAKE, 10, MISALIGNED,
-                              ctypes.c_float(0.01), None) == ctr.CTR_ERR_UNSUPPORTED
+                              ctypes.c_float(0.01), 0, s0, None) == ctr.CTR_ERR_UNSUPPORTED
     assert lib.ctr_gather_rows(FAKE, 0, 100, 16, None, FAKE, 10, FAKE, None) == \
         ctr.CTR_ERR_INVALID_ARGUMENT
     rb = (ctypes.c_int64 * 3)(0, 10, 5)                    # decreasing
-    assert lib.ctr_init_table_hash(FAKE, 0, 16, ctypes.cast(rb, ctypes.c_void_p), 2,
-                                   ctypes.c_uint64(1), None) == ctr.CTR_ERR_INVALID_ARGUMENT
+    assert lib.ctr_init_tables_hash(FAKE, 0, 16, ctypes.cast(rb, ctypes.c_void_p), 2,
+                                    ctypes.c_uint64(1), None) == ctr.CTR_ERR_INVALID_ARGUMENT
     assert lib.ctr_validate_csr(FAKE, 1, 10, None, 10, 1, None, 100, FAKE, None) == \
         ctr.CTR_ERR_INVALID_ARGUMENT
 
 
-def test_stochastic_rounding_entry_points_bad_args():
+def test_rounding_argument_bad_args():
     lib = _lib()
     s0 = ctypes.c_uint64(7)
-    # fp32 tables have no stochastic rounding
-    st = lib.ctr_sparse_sgd_sr(FAKE, ctr.CTR_F32, 100, 16, FAKE, FAKE, 10, FAKE,
-                               ctypes.c_float(0.01), s0, None)
-    assert st == ctr.CTR_ERR_UNSUPPORTED and b"BF16" in lib.ctr_last_error()
-    assert lib.ctr_sparse_sgd_sr(FAKE, ctr.CTR_BF16, 100, 16, FAKE, FAKE, 10, FAKE,
-                                 ctypes.c_float(float("inf")), s0, None) == \
+    SR = ctr.CTR_ROUND_STOCHASTIC
+    # fp32 tables have no stochastic rounding; an unknown rounding code
+    st = lib.ctr_sparse_sgd(FAKE, ctr.CTR_F32, 100, 16, FAKE, FAKE, 10, FAKE,
+                            ctypes.c_float(0.01), SR, s0, None)
+    assert st == ctr.CTR_ERR_UNSUPPORTED and b"BF16" in lib.ctr_last_error_message()
+    assert lib.ctr_sparse_sgd(FAKE, ctr.CTR_BF16, 100, 16, FAKE, FAKE, 10, FAKE,
+                              ctypes.c_float(float("inf")), SR, s0, None) == \
         ctr.CTR_ERR_INVALID_ARGUMENT
+    assert lib.ctr_sparse_sgd(FAKE, ctr.CTR_BF16, 100, 16, FAKE, FAKE, 10, FAKE,
+                              ctypes.c_float(0.01), 5, s0, None) == ctr.CTR_ERR_INVALID_ARGUMENT
+    assert b"rounding" in lib.ctr_last_error_message()
     wsb = ctypes.c_size_t(0)
-    st = lib.ctr_embbag_bwd_sgd_sr(FAKE, 64, 0, FAKE, 10, 1, 100, FAKE, FAKE, FAKE, ctr.CTR_F32,
-                                   1000, 16, FAKE, ctypes.c_float(0.01), s0, None, None,
-                                   ctypes.byref(wsb), None)
+    bwd = lib.ctr_embbag_bwd_sgd
+    st = bwd(FAKE, ctr.CTR_F32, 64, 0, FAKE, 10, 1, 100, FAKE, FAKE, FAKE, ctr.CTR_F32, 1000, 16,
+             FAKE, ctypes.c_float(0.01), SR, s0, None, None, ctypes.byref(wsb), None)
     assert st == ctr.CTR_ERR_UNSUPPORTED
-    assert lib.ctr_embbag_bwd_sgd_sr(None, 64, 0, None, 10, 1, 100, None, None, FAKE,
-                                     ctr.CTR_BF16, 1000, 16, None, ctypes.c_float(0.01), s0,
-                                     None, None, ctypes.byref(wsb), None) == ctr.CTR_OK
+    assert bwd(FAKE, ctr.CTR_F32, 64, 0, FAKE, 10, 1, 100, FAKE, FAKE, FAKE, ctr.CTR_BF16, 1000,
+               16, FAKE, ctypes.c_float(0.01), 9, s0, None, None, ctypes.byref(wsb), None) == \
+        ctr.CTR_ERR_INVALID_ARGUMENT
+    assert bwd(FAKE, 4, 64, 0, FAKE, 10, 1, 100, FAKE, FAKE, FAKE, ctr.CTR_BF16, 1000, 16, FAKE,
+               ctypes.c_float(0.01), 0, s0, None, None, ctypes.byref(wsb), None) == \
+        ctr.CTR_ERR_INVALID_ARGUMENT
+    assert b"grad_dtype" in lib.ctr_last_error_message()
+    assert bwd(None, ctr.CTR_F32, 64, 0, None, 10, 1, 100, None, None, FAKE, ctr.CTR_BF16, 1000,
+               16, None, ctypes.c_float(0.01), SR, s0, None, None, ctypes.byref(wsb), None) == \
+        ctr.CTR_OK
     assert wsb.value > 0                          # the workspace query of ctr_embbag_bwd
 
 
@@ -223,11 +240,12 @@ def test_interaction_variant_bad_args():
     f = lib.ctr_dot_interaction_self_fwd
     # F = 5, dim = 16: the self-dot set needs dim + 15 columns, the strict one dim + 10
     assert f(FAKE, 10, 5, 16, ctr.CTR_F32, FAKE, 16 + 10, None) == ctr.CTR_ERR_INVALID_ARGUMENT
-    assert b"stride" in lib.ctr_last_error()
+    assert b"stride" in lib.ctr_last_error_message()
     assert f(FAKE, 10, 0, 16, ctr.CTR_F32, FAKE, 100, None) == ctr.CTR_ERR_INVALID_ARGUMENT
     assert f(FAKE, 10, 5, 24, ctr.CTR_BF16, FAKE, 100, None) == ctr.CTR_ERR_UNSUPPORTED
     b = lib.ctr_dot_interaction_self_bwd
-    assert b(FAKE, None, 31, 10, 5, 16, ctr.CTR_F32, FAKE, None) == ctr.CTR_ERR_INVALID_ARGUMENT
+    assert b(FAKE, None, 31, 10, 5, 16, ctr.CTR_F32, ctr.CTR_F32, FAKE, None) == \
+        ctr.CTR_ERR_INVALID_ARGUMENT
     assert lib.ctr_fm_interaction_fwd(FAKE, 10, 0, 16, FAKE, None) == \
         ctr.CTR_ERR_INVALID_ARGUMENT
     assert lib.ctr_fm_interaction_bwd(FAKE, None, 10, 3, 16, FAKE, None) == \
@@ -243,7 +261,7 @@ def test_dictionary_bad_args():
         ctr.CTR_ERR_INVALID_ARGUMENT
     assert lib.ctr_dict_build(FAKE, FAKE, None, 16, FAKE, 16, st32, None) == \
         ctr.CTR_ERR_INVALID_ARGUMENT
-    assert b"capacity" in lib.ctr_last_error()
+    assert b"capacity" in lib.ctr_last_error_message()
     assert lib.ctr_dict_build(FAKE, FAKE, None, 10, MISALIGNED, 16, st32, None) == \
         ctr.CTR_ERR_UNSUPPORTED
     assert lib.ctr_dict_lookup(FAKE, 10, FAKE, 100, FAKE, None) == ctr.CTR_ERR_INVALID_ARGUMENT
@@ -311,7 +329,7 @@ def test_step_run_bad_args():
     assert lib.ctr_step_run_deep(ctypes.byref(d), 0, None, FAKE, FAKE,
                                  ctypes.cast(ev6, ctypes.c_void_p), None, None) == \
         ctr.CTR_ERR_INVALID_ARGUMENT
-    assert b"workspace" in lib.ctr_last_error()
+    assert b"workspace" in lib.ctr_last_error_message()
 
 
 
@@ -387,7 +405,7 @@ def test_noalloc_backward_limits_and_rejections():
     args = (FAKE, 1, 65 * 128, 128, FAKE, 32768, 64, 67_000_000, FAKE, FAKE, FAKE, 1,
             256_000_000, 128, FAKE, ctypes.c_float(0.01), 0, ctypes.c_uint64(0), None, None)
     assert lib.ctr_embbag_bwd_sgd_noalloc(*args) == 2          # CTR_ERR_UNSUPPORTED
-    assert b"scratch" in lib.ctr_last_error()
+    assert b"scratch" in lib.ctr_last_error_message()
     bad = list(args)
     bad[1] = 7                                                 # unknown gradient dtype
     assert lib.ctr_embbag_bwd_sgd_noalloc(*bad) == 1

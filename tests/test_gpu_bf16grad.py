@@ -71,10 +71,10 @@ def test_bf16_gradients_sum_like_their_fp32_widening(name):
         ta = gpu_table(w.rows, d, w.dtype, 9)
         tb = gpu_table(w.rows, d, w.dtype, 9)
         if sr:
-            ctr.ctr_embbag_bwd_sgd_sr(g16[:, 1:, :], (T + 1) * d, d, off, B, T, w.nnz, src, nu,
-                                      ta, uq, 0.05, 1234)
-            ctr.ctr_embbag_bwd_sgd_sr(g32[:, 1:, :], (T + 1) * d, d, off, B, T, w.nnz, src, nu,
-                                      tb, uq, 0.05, 1234)
+            ctr.ctr_embbag_bwd_sgd(g16[:, 1:, :], (T + 1) * d, d, off, B, T, w.nnz, src, nu,
+                                   ta, uq, 0.05, rounding=ctr.CTR_ROUND_STOCHASTIC, seed=1234)
+            ctr.ctr_embbag_bwd_sgd(g32[:, 1:, :], (T + 1) * d, d, off, B, T, w.nnz, src, nu,
+                                   tb, uq, 0.05, rounding=ctr.CTR_ROUND_STOCHASTIC, seed=1234)
         else:
             ctr.ctr_embbag_bwd_sgd(g16[:, 1:, :], (T + 1) * d, d, off, B, T, w.nnz, src, nu,
                                    ta, uq, 0.05)

@@ -69,7 +69,7 @@ def _pool_setup(dtype, dim, seed=11):
     w = workloads.dictionary(seed=seed, batch=512, slots=100, entries=200_000, hot=20_000)
     tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
     table = torch.empty((w.entries, dim), dtype=tdt, device=DEV)
-    ctr.ctr_init_table_hash(table, [w.entries], w.table_seed)
+    ctr.ctr_init_tables_hash(table, [w.entries], w.table_seed)
     # the cache holds copies of the rows of the H most popular IDs, slot = rank - 1
     hot_rows = table[dev(w.dict_rows[:w.hot].astype(np.int64))].contiguous()
     slots, status = ctr.ctr_dict_build(dev(w.dict_keys), dev(w.dict_rows), dev(w.hot_slots),

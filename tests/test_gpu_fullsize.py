@@ -335,7 +335,7 @@ def test_large_sgd_hot_rows(large_run):
     the oracle's update of the same rows.  Runs last: it overwrites the stepped table."""
     w, fe = large_run
     B, T, d = w.batch, w.num_tables, w.dim
-    ctr.ctr_init_table_hash(fe.table, w.rows, w.table_seed)
+    ctr.ctr_init_tables_hash(fe.table, w.rows, w.table_seed)
     rng = np.random.default_rng(6)
     dY = torch.from_numpy(rng.standard_normal((B, T, d), dtype=np.float32)).to(torch.bfloat16)
     dYd = dY.to(DEV)

@@ -53,7 +53,7 @@ def rand_csr(rng, T, B, rows, max_len, empty_frac=0.0):
 def gpu_table(rows, dim, dtype, seed):
     t = torch.empty((int(sum(rows)), dim),
                     dtype=torch.bfloat16 if dtype == "bf16" else torch.float32, device=DEV)
-    ctr.ctr_init_table_hash(t, rows, seed)
+    ctr.ctr_init_tables_hash(t, rows, seed)
     return t
 
 

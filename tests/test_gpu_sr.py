@@ -1,10 +1,10 @@
 """Stochastic rounding of the bf16 sparse update ("DHEN" notes, 6.4 "Common Optimizations")
 on the GPU, through the C ABI.
 
-* ctr_sparse_sgd_sr against the oracle, bit for bit.  Both sides take the rounding decision
+* ctr_sparse_sgd with CTR_ROUND_STOCHASTIC against the oracle, bit for bit.  Both sides take the rounding decision
   on the same binary32 value, a fused multiply-add, with the same counter-based bits.
-* The fused backward, ctr_embbag_bwd_sgd_sr, is bit-identical to ctr_embbag_bwd followed by
-  ctr_sparse_sgd_sr with the same seed.  Every value it stores is a bf16 neighbour of the
+* The fused backward, ctr_embbag_bwd_sgd with CTR_ROUND_STOCHASTIC, is bit-identical to
+  ctr_embbag_bwd followed by ctr_sparse_sgd with the same rounding and seed.  Every value it stores is a bf16 neighbour of the
   oracle's exact update.
 * ctr_step_run with rounding = CTR_ROUND_STOCHASTIC matches the same steps driven call by
   call, with the same per-step seeds.
@@ -42,7 +42,8 @@ def test_sparse_sgd_sr_bit_exact(dim):
     gg = np.zeros((cap, dim), np.float32)
     gg[:U] = g
     seed = 0xC0FFEE ^ dim
-    ctr.ctr_sparse_sgd_sr(t, dev(uq), dev(np.array([U], np.int32)), cap, dev(gg), 0.01, seed)
+    ctr.ctr_sparse_sgd(t, dev(uq), dev(np.array([U], np.int32)), cap, dev(gg), 0.01,
+                       ctr.CTR_ROUND_STOCHASTIC, seed)
     after = host(t.float())
     want = orc.sparse_sgd_sr(tab, uniq, g, 0.01, seed)
     np.testing.assert_array_equal(after[uniq], want)

@@ -1,5 +1,5 @@
 """ctr_embbag_bwd_sgd_noalloc (the backward + SGD entry that allocates nothing: its carries
-live in the library's per-GPU scratch array) against ctr_embbag_bwd_sgd_ex (same kernels,
+live in the library's per-GPU scratch array) against ctr_embbag_bwd_sgd (same kernels,
 caller workspace): bit-identical row sums and updated tables, on consecutive calls that
 reuse the scratch, the later ones with smaller inputs."""
 import sys
