@@ -75,8 +75,29 @@ double orc_round_bf16(double x) {
   return r;
 }
 
+/* Round a double to the nearest IEEE binary16 value (11 significant bits, exponents down to
+ * -14, subnormal quantum 2^-24, largest finite 65504), ties to even, returned as a double.
+ * The same construction as orc_round_bf16: keep 11 bits of m in x = m * 2^e with rint, the
+ * quantum no finer than 2^-24; a result beyond 65504 is infinity.  ("DHEN" notes, 6.4 names
+ * FP16 embedding storage.) */
+double orc_round_f16(double x) {
+  if (x == 0.0 || isnan(x) || isinf(x)) return x;
+  int e;
+  frexp(x, &e);
+  int q = e - 11;                /* exponent of the last kept bit */
+  if (q < -24) q = -24;          /* subnormal binary16 quantum */
+  double r = ldexp(rint(ldexp(x, -q)), q);
+  if (fabs(r) > 65504.0) r = copysign(INFINITY, x);
+  return r;
+}
+
 /* Round a double to binary32, ties to even (C conversion in the default rounding mode). */
 double orc_round_f32(double x) { return (double)(float)x; }
+
+/* Storage types of a table: 0 binary32, 1 bfloat16, 2 binary16 (the C ABI's dtype codes). */
+static double round_store(double x, int32_t stype) {
+  return stype == 1 ? orc_round_bf16(x) : stype == 2 ? orc_round_f16(x) : orc_round_f32(x);
+}
 
 /* ------------------------------------------------------------------ table fill */
 /* splitmix64 (Steele, Lea, Flood, "Fast splittable pseudorandom number generators",
@@ -91,16 +112,16 @@ uint64_t orc_splitmix64_next(uint64_t* state) {
 
 /* Table element (global_row, col): one splitmix64 output from state seed ^ (row*dim+col);
  * its top 24 bits give u in [0,1); x = fp32(2u-1) * fp32(1/sqrt(rows_t)) in binary32;
- * bf16 storage rounds x to nearest-even.  Returns the stored value. */
+ * bf16 and fp16 storage (stype 1, 2) round x to nearest-even.  Returns the stored value. */
 double orc_table_value(uint64_t seed, int64_t global_row, int64_t col, int32_t dim,
-                       int64_t rows_t, int32_t bf16) {
+                       int64_t rows_t, int32_t stype) {
   uint64_t st = seed ^ (uint64_t)(global_row * (int64_t)dim + col);
   uint64_t v = orc_splitmix64_next(&st);
   double u = (double)(v >> 40) * (1.0 / 16777216.0);
   float a = (float)(1.0 / sqrt((double)rows_t));
   float s = (float)(2.0 * u - 1.0);
   float x = s * a;
-  return bf16 ? orc_round_bf16((double)x) : (double)x;
+  return round_store((double)x, stype);
 }
 
 typedef struct {
@@ -109,7 +130,7 @@ typedef struct {
   const int64_t* row_base;  /* [num_tables + 1] */
   int32_t num_tables;
   int32_t dim;
-  int32_t bf16;
+  int32_t stype;            /* storage type: 0 binary32, 1 bfloat16, 2 binary16 */
 } orc_table;
 
 static int64_t rows_of_key(const orc_table* tb, int64_t key) {
@@ -121,13 +142,13 @@ static int64_t rows_of_key(const orc_table* tb, int64_t key) {
 
 static double tval(const orc_table* tb, int64_t key, int64_t col) {
   if (tb->data) return (double)tb->data[key * (int64_t)tb->dim + col];
-  return orc_table_value(tb->seed, key, col, tb->dim, rows_of_key(tb, key), tb->bf16);
+  return orc_table_value(tb->seed, key, col, tb->dim, rows_of_key(tb, key), tb->stype);
 }
 
 /* Fill rows `keys[0..n)` of the described table into out[n][dim] (as stored values). */
 void orc_table_rows(uint64_t seed, const int64_t* row_base, int32_t num_tables, int32_t dim,
-                    int32_t bf16, const int64_t* keys, int64_t n, float* out) {
-  orc_table tb = {NULL, seed, row_base, num_tables, dim, bf16};
+                    int32_t stype, const int64_t* keys, int64_t n, float* out) {
+  orc_table tb = {NULL, seed, row_base, num_tables, dim, stype};
 #pragma omp parallel for schedule(static)
   for (int64_t r = 0; r < n; ++r)
     for (int64_t c = 0; c < dim; ++c) out[r * dim + c] = (float)tval(&tb, keys[r], c);
@@ -203,9 +224,9 @@ int64_t orc_unique(const int64_t* keys, int64_t n, int64_t* uniq, int32_t* inver
 /* [TN] "Core Optimizations": fetch the batch's rows into the batch-sized matrix,
  * E[u] = W[rows[u]]. */
 void orc_gather_rows(const float* data, uint64_t seed, const int64_t* row_base,
-                     int32_t num_tables, int32_t dim, int32_t bf16, const int64_t* rows,
+                     int32_t num_tables, int32_t dim, int32_t stype, const int64_t* rows,
                      int64_t n, double* out) {
-  orc_table tb = {data, seed, row_base, num_tables, dim, bf16};
+  orc_table tb = {data, seed, row_base, num_tables, dim, stype};
 #pragma omp parallel for schedule(static)
   for (int64_t u = 0; u < n; ++u)
     for (int64_t c = 0; c < dim; ++c) out[u * dim + c] = tval(&tb, rows[u], c);
@@ -216,9 +237,9 @@ void orc_gather_rows(const float* data, uint64_t seed, const int64_t* row_base,
  * occurrence counted, empty bag = 0).  out and mag are [batch][num_tables][dim].
  * Row of occurrence i: key = row_base[t] + ids[i] (ids are table-local rows here). */
 void orc_embbag_fwd(const float* data, uint64_t seed, const int64_t* row_base,
-                    int32_t num_tables, int32_t dim, int32_t bf16, const int64_t* ids,
+                    int32_t num_tables, int32_t dim, int32_t stype, const int64_t* ids,
                     const int64_t* offsets, int64_t batch, double* out, double* mag) {
-  orc_table tb = {data, seed, row_base, num_tables, dim, bf16};
+  orc_table tb = {data, seed, row_base, num_tables, dim, stype};
 #pragma omp parallel for schedule(dynamic, 64)
   for (int64_t s = 0; s < (int64_t)num_tables * batch; ++s) {
     int64_t t = s / batch, b = s % batch;
@@ -342,20 +363,20 @@ void orc_embbag_bwd(const double* dY, const double* dymag, const int64_t* offset
 
 /* ------------------------------------------------------------------ a9: sparse SGD */
 /* W[uniq[u]] <- W[uniq[u]] - lr * g[u] in double, rounded once to the storage type
- * (binary32, or bfloat16 nearest-even).  Rows not in uniq are untouched by definition.
+ * (binary32, or bfloat16 / binary16 nearest-even).  Rows not in uniq are untouched by definition.
  * new_rows, nmag: [U][dim] (nmag = |W| + lr * gmag). */
 void orc_sparse_sgd(const float* data, uint64_t seed, const int64_t* row_base,
-                    int32_t num_tables, int32_t dim, int32_t bf16, const int64_t* uniq,
+                    int32_t num_tables, int32_t dim, int32_t stype, const int64_t* uniq,
                     int64_t U, const double* g, const double* gmag, float lr,
                     double* new_rows, double* nmag) {
-  orc_table tb = {data, seed, row_base, num_tables, dim, bf16};
+  orc_table tb = {data, seed, row_base, num_tables, dim, stype};
   double l = (double)lr;
 #pragma omp parallel for schedule(static)
   for (int64_t u = 0; u < U; ++u)
     for (int64_t c = 0; c < dim; ++c) {
       double w = tval(&tb, uniq[u], c);
       double x = w - l * g[u * dim + c];
-      new_rows[u * dim + c] = bf16 ? orc_round_bf16(x) : orc_round_f32(x);
+      new_rows[u * dim + c] = round_store(x, stype);
       nmag[u * dim + c] = fabs(w) + l * gmag[u * dim + c];
     }
 }
@@ -633,10 +654,10 @@ void orc_dict_lookup(const int64_t* keys, const int32_t* rows, const int32_t* ho
  * of dictionary rows, so the cached or the table copy is the same value).  W is the
  * dictionary table (one table of num_rows rows, the counter-based fill or `data`). */
 void orc_dict_pool(const float* data, uint64_t seed, int64_t num_rows, int32_t dim,
-                   int32_t bf16, const int64_t* values, const int64_t* offsets, int64_t batch,
+                   int32_t stype, const int64_t* values, const int64_t* offsets, int64_t batch,
                    int32_t num_tables, double* out, double* omag) {
   int64_t rb[2] = {0, num_rows};
-  orc_table tb = {data, seed, rb, 1, dim, bf16};
+  orc_table tb = {data, seed, rb, 1, dim, stype};
   int64_t nb = (int64_t)num_tables * batch;
 #pragma omp parallel for schedule(static)
   for (int64_t s = 0; s < nb; ++s) {
@@ -683,6 +704,27 @@ double orc_sr_bf16(double x, uint32_t r) {
   return out;
 }
 
+/* The same rule for binary16 storage ("DHEN" notes, 6.4: FP16 embeddings with stochastic
+ * rounding): lo is x truncated toward zero to binary16 (11 significant bits, quantum no finer
+ * than 2^-24), hi iff r < p * 2^16.  Here p can carry more than 16 bits (13 bits are dropped
+ * in the normal range, up to 125 below it), so SR(x) averages to x plus at most quantum *
+ * 2^-16 over the 2^16 values of r: the comparison rounds the probability up to a multiple of
+ * 2^-16.  Zeros, infinities and NaN come back unchanged; anything whose result exceeds the
+ * largest finite binary16, 65504, becomes infinity (so |x| >= 65536 always does). */
+double orc_sr_f16(double x, uint32_t r) {
+  if (x == 0.0 || isnan(x) || isinf(x)) return x;
+  int e;
+  frexp(x, &e);
+  int q = e - 11;                /* exponent of the last kept bit, as in orc_round_f16 */
+  if (q < -24) q = -24;
+  double quantum = ldexp(1.0, q);
+  double lo = ldexp(trunc(ldexp(x, -q)), q);
+  double p = (fabs(x) - fabs(lo)) / quantum;       /* exact, in [0, 1) */
+  double out = ((double)r < p * 65536.0) ? lo + copysign(quantum, x) : lo;
+  if (fabs(out) > 65504.0) out = copysign(INFINITY, x);
+  return out;
+}
+
 /* Random bits of element (key, col) of an update drawn with seed s: columns are taken in
  * groups of four, c4 = col - col mod 4; one splitmix64 output from state s ^ (key*dim + c4)
  * (the same generator as the table fill, a fresh seed per update) gives 64 bits, and
@@ -693,19 +735,20 @@ uint32_t orc_sr_bits(uint64_t seed, int64_t key, int64_t col, int32_t dim) {
   return (uint32_t)((orc_splitmix64_next(&st) >> (16 * e)) & 0xFFFFu);
 }
 
-/* a9 with stochastic rounding, bfloat16 storage: W[uniq[u]] <- SR(x) with
- * x = fmaf(-lr, g[u], W[uniq[u]]), the binary32 fused multiply-add rounded once.  The value
- * that decides the rounding is taken in binary32, the precision the update kernel computes
- * in (g is binary32 here).  new_rows: [U][dim]. */
+/* a9 with stochastic rounding, bfloat16 (stype 1) or binary16 (stype 2) storage:
+ * W[uniq[u]] <- SR(x) with x = fmaf(-lr, g[u], W[uniq[u]]), the binary32 fused multiply-add
+ * rounded once.  The value that decides the rounding is taken in binary32, the precision the
+ * update kernel computes in (g is binary32 here).  new_rows: [U][dim]. */
 void orc_sparse_sgd_sr(const float* data, uint64_t seed, const int64_t* row_base,
-                       int32_t num_tables, int32_t dim, const int64_t* uniq, int64_t U,
-                       const float* g, float lr, uint64_t sr_seed, double* new_rows) {
-  orc_table tb = {data, seed, row_base, num_tables, dim, 1};
+                       int32_t num_tables, int32_t dim, int32_t stype, const int64_t* uniq,
+                       int64_t U, const float* g, float lr, uint64_t sr_seed, double* new_rows) {
+  orc_table tb = {data, seed, row_base, num_tables, dim, stype};
 #pragma omp parallel for schedule(static)
   for (int64_t u = 0; u < U; ++u)
     for (int64_t c = 0; c < dim; ++c) {
       float w = (float)tval(&tb, uniq[u], c);
       float x = fmaf(-lr, g[u * dim + c], w);
-      new_rows[u * dim + c] = orc_sr_bf16((double)x, orc_sr_bits(sr_seed, uniq[u], c, dim));
+      uint32_t r = orc_sr_bits(sr_seed, uniq[u], c, dim);
+      new_rows[u * dim + c] = stype == 2 ? orc_sr_f16((double)x, r) : orc_sr_bf16((double)x, r);
     }
 }

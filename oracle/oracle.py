@@ -74,8 +74,10 @@ def _load():
         "orc_dict_lookup": (None, [P, P, P, P, i64, P, i64, P]),
         "orc_dict_pool": (None, [P, u64, i64, i32, i32, P, P, i64, i32, P, P]),
         "orc_sr_bf16": (f64, [f64, ctypes.c_uint32]),
+        "orc_round_f16": (f64, [f64]),
+        "orc_sr_f16": (f64, [f64, ctypes.c_uint32]),
         "orc_sr_bits": (ctypes.c_uint32, [u64, i64, i64, i32]),
-        "orc_sparse_sgd_sr": (None, [P, u64, P, i32, i32, P, i64, P, f32, u64, P]),
+        "orc_sparse_sgd_sr": (None, [P, u64, P, i32, i32, i32, P, i64, P, f32, u64, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -102,6 +104,9 @@ def get_threads() -> int:
 
 
 # ------------------------------------------------------------------------ tables
+STYPES = {"f32": 0, "bf16": 1, "f16": 2}      # table storage codes (the C ABI's dtype codes)
+
+
 class Table:
     """An embedding table as the oracle sees it: either explicit fp32 values
     (``data`` [total_rows, dim]) or the counter-based fill regenerated on demand."""
@@ -110,7 +115,8 @@ class Table:
                  data: Optional[np.ndarray] = None):
         self.rows = [int(r) for r in rows]
         self.dim = int(dim)
-        self.bf16 = 1 if dtype == "bf16" else 0
+        self.dtype = dtype
+        self.stype = STYPES[dtype]                # storage code: 0 f32, 1 bf16, 2 f16
         self.seed = int(seed) & 0xFFFFFFFFFFFFFFFF
         rb = np.zeros(len(self.rows) + 1, dtype=np.int64)
         rb[1:] = np.cumsum(np.asarray(self.rows, dtype=np.int64))
@@ -126,7 +132,8 @@ class Table:
         return int(self.row_base[-1])
 
     def args(self):
-        return (_p(self.data), self.seed, _p(self.row_base), self.num_tables, self.dim, self.bf16)
+        return (_p(self.data), self.seed, _p(self.row_base), self.num_tables, self.dim,
+                self.stype)
 
 
 def splitmix64_stream(state: int, count: int) -> list:
@@ -135,20 +142,26 @@ def splitmix64_stream(state: int, count: int) -> list:
     return [int(lib.orc_splitmix64_next(ctypes.byref(st))) for _ in range(count)]
 
 
-def table_value(seed: int, global_row: int, col: int, dim: int, rows_t: int, bf16: bool) -> float:
+def table_value(seed: int, global_row: int, col: int, dim: int, rows_t: int,
+                dtype: str = "f32") -> float:
     return float(_load().orc_table_value(seed & 0xFFFFFFFFFFFFFFFF, global_row, col, dim,
-                                         rows_t, int(bool(bf16))))
+                                         rows_t, STYPES[dtype]))
 
 
 def round_bf16(x: float) -> float:
     return float(_load().orc_round_bf16(float(x)))
 
 
+def round_f16(x: float) -> float:
+    """x rounded to the nearest IEEE binary16 value, ties to even (as a float)."""
+    return float(_load().orc_round_f16(float(x)))
+
+
 def table_rows(tab: Table, keys: np.ndarray) -> np.ndarray:
     """Stored values of rows ``keys`` (global row ids) as fp32 [len(keys), dim]."""
     keys = _c(keys, np.int64)
     out = np.empty((keys.size, tab.dim), dtype=np.float32)
-    _load().orc_table_rows(tab.seed, _p(tab.row_base), tab.num_tables, tab.dim, tab.bf16,
+    _load().orc_table_rows(tab.seed, _p(tab.row_base), tab.num_tables, tab.dim, tab.stype,
                            _p(keys), keys.size, _p(out))
     return out
 
@@ -361,15 +374,20 @@ def sr_bits(seed: int, key: int, col: int, dim: int) -> int:
     return int(_load().orc_sr_bits(seed & 0xFFFFFFFFFFFFFFFF, int(key), int(col), int(dim)))
 
 
+def sr_f16(x: float, r: int) -> float:
+    """Stochastic rounding of x to binary16 with the 16-bit random integer r."""
+    return float(_load().orc_sr_f16(float(x), int(r) & 0xFFFF))
+
+
 def sparse_sgd_sr(tab: Table, uniq, g, lr: float, sr_seed: int):
-    """Updated stored values (bf16 table) of rows ``uniq`` with stochastic rounding:
+    """Updated stored values (bf16 or fp16 table) of rows ``uniq`` with stochastic rounding:
     SR(fmaf(-lr, g, w)) per element, g binary32 [U, dim].  Returns float64 [U, dim]."""
-    assert tab.bf16, "stochastic rounding is defined for bf16 storage"
+    assert tab.stype in (1, 2), "stochastic rounding is defined for 16-bit storage"
     uniq = _c(uniq, np.int64)
     g = _c(g, np.float32)
     U = uniq.size
     out = np.empty((U, tab.dim), dtype=np.float64)
-    _load().orc_sparse_sgd_sr(*tab.args()[:5], _p(uniq), U, _p(g), ctypes.c_float(lr),
+    _load().orc_sparse_sgd_sr(*tab.args(), _p(uniq), U, _p(g), ctypes.c_float(lr),
                               ctypes.c_uint64(sr_seed & 0xFFFFFFFFFFFFFFFF), _p(out))
     return out
 
@@ -395,6 +413,6 @@ def dict_pool(tab: "Table", values, offsets, batch: int, num_tables: int):
     offsets = _c(offsets, np.int64)
     out = np.empty((batch, num_tables, tab.dim), dtype=np.float64)
     om = np.empty_like(out)
-    _load().orc_dict_pool(_p(tab.data), tab.seed, tab.total_rows, tab.dim, tab.bf16, _p(values),
+    _load().orc_dict_pool(_p(tab.data), tab.seed, tab.total_rows, tab.dim, tab.stype, _p(values),
                           _p(offsets), batch, num_tables, _p(out), _p(om))
     return out, om

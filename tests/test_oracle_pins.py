@@ -61,7 +61,8 @@ def test_round_bf16_matches_torch_and_brute_force():
 
 def test_table_value_definition():
     seed, dim = 12345, 8
-    for rows_t, bf16 in [(1000, False), (4_000_000, True), (20_000_000, False)]:
+    for rows_t, dtype in [(1000, "f32"), (4_000_000, "bf16"), (20_000_000, "f32"),
+                          (30_000, "f16")]:
         a = np.float32(1.0 / math.sqrt(rows_t))
         for r in [0, 1, 7, rows_t - 1]:
             for c in [0, 3, dim - 1]:
@@ -69,8 +70,9 @@ def test_table_value_definition():
                 v = orc.splitmix64_stream(st, 1)[0]
                 u = (v >> 40) / float(1 << 24)
                 x = np.float32(np.float32(2.0 * u - 1.0) * a)
-                want = orc.round_bf16(float(x)) if bf16 else float(x)
-                got = orc.table_value(seed, r, c, dim, rows_t, bf16)
+                want = {"f32": float(x), "bf16": orc.round_bf16(float(x)),
+                        "f16": float(np.float16(x))}[dtype]
+                got = orc.table_value(seed, r, c, dim, rows_t, dtype)
                 assert got == want
                 assert -a <= got <= a
 
