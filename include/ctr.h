@@ -39,7 +39,8 @@
  *     stores the required byte count in *workspace_bytes and returns CTR_OK.  A workspace
  *     must be 16-byte aligned (CTR_ERR_UNSUPPORTED otherwise).
  *   - Tables: all tables of a model live in ONE row-major allocation [total_rows, dim] of
- *     fp32 or bf16 (16-byte aligned); table t owns rows [row_base[t], row_base[t+1]).
+ *     fp32, bf16 or fp16 (16-byte aligned); table t owns rows [row_base[t], row_base[t+1]).
+ *     Reads widen the stored values to fp32 exactly.
  *     Bags are CSR, table-major: bag (t, b) spans indices[offsets[t*batch+b] ..
  *     offsets[t*batch+b+1]).
  */
@@ -61,7 +62,9 @@ typedef enum {
   CTR_ERR_HIP = 4
 } ctr_status_t;
 
-typedef enum { CTR_F32 = 0, CTR_BF16 = 1 } ctr_dtype_t;
+/* Element types.  Tables: CTR_F32, CTR_BF16 or CTR_F16 (IEEE binary16, "DHEN" notes 6.4: FP16
+ * embeddings); gradients, interaction operands and dZ: CTR_F32 or CTR_BF16. */
+typedef enum { CTR_F32 = 0, CTR_BF16 = 1, CTR_F16 = 2 } ctr_dtype_t;
 typedef enum { CTR_I32 = 0, CTR_I64 = 1 } ctr_index_t;
 
 /* Library version (major*10000 + minor*100 + patch). */
@@ -204,7 +207,7 @@ int32_t ctr_embbag_bwd_sgd_noalloc(const void* grad, int32_t grad_dtype, int64_t
 size_t ctr_embbag_bwd_noalloc_scratch_bytes(int64_t nnz, int32_t dim);
 size_t ctr_noalloc_scratch_capacity(void);
 
-/* Rounding of an SGD store into a bf16 table. */
+/* Rounding of an SGD store into a 16-bit (bf16 or fp16) table. */
 enum { CTR_ROUND_NEAREST = 0, CTR_ROUND_STOCHASTIC = 1 };
 
 /*
@@ -214,18 +217,23 @@ enum { CTR_ROUND_NEAREST = 0, CTR_ROUND_STOCHASTIC = 1 };
  * no two threads touch one row; untouched rows stay bit-identical.  Element (key, c),
  * key = uniq[u]: x = fmaf(-lr, row_grads[u, c], table[key, c]) (binary32, rounded once),
  * then stored by `rounding`:
- *   CTR_ROUND_NEAREST     x itself (fp32 table), or x rounded to bf16 nearest-even; `seed`
- *                         is ignored.
- *   CTR_ROUND_STOCHASTIC  bf16 table only ("DHEN" notes, 6.4 "Common Optimizations":
- *                         low-precision embeddings updated with stochastic rounding):
+ *   CTR_ROUND_NEAREST     x itself (fp32 table), or x rounded to bf16 / fp16 nearest-even
+ *                         (fp16: beyond 65504 rounds to infinity, below 2^-14 to the
+ *                         subnormal grid); `seed` is ignored.
+ *   CTR_ROUND_STOCHASTIC  bf16 or fp16 table ("DHEN" notes, 6.4 "Common Optimizations":
+ *                         FP16 embeddings updated with stochastic rounding):
  *       r = bits 16e .. 16e+15 (e = c mod 4) of splitmix64 from state
  *           seed ^ (key * dim + c - e)          (one generator output per 4 columns)
- *       stored = lo + sign(x) * ulp   if r < the low 16 bits of x's binary32 pattern
+ *       lo = x truncated toward zero to the table type, q = that type's spacing at lo
+ *       stored = lo + sign(x) * q     if r < 2^16 * (|x| - |lo|) / q
  *                lo                   otherwise
- *     where lo is x truncated toward zero to bf16: round away from zero with probability
- *     (|x| - |lo|) / ulp, so the stored value is x in expectation over r.  Exact values and
- *     infinities are kept, NaN stays NaN.  Use a fresh seed per update (ctr_sr_step_seed).
- *     A CTR_F32 table gives CTR_ERR_UNSUPPORTED.
+ *     i.e. round away from zero with probability (|x| - |lo|) / q, rounded up to a multiple
+ *     of 2^-16 (exact for bf16, where the threshold is the low 16 bits of x's binary32
+ *     pattern; fp16 drops 13 bits in its normal range, so the threshold is those bits times
+ *     8), so the stored value is x in expectation over r to within q * 2^-16.  Exact values
+ *     and infinities are kept, NaN stays NaN; a result beyond the type's largest finite value
+ *     (fp16: |x| >= 65536, or rounding up from (65504, 65536)) is infinity.  Use a fresh seed
+ *     per update (ctr_sr_step_seed).  A CTR_F32 table gives CTR_ERR_UNSUPPORTED.
  */
 int32_t ctr_sparse_sgd(void* table, int32_t dtype, int64_t total_rows, int32_t dim,
                        const int64_t* uniq, const int32_t* num_unique, int64_t capacity,
@@ -259,11 +267,12 @@ int32_t ctr_dot_interaction_fwd(const float* Z, int64_t batch, int32_t num_vecto
  * vectors instead of a second read of Z; with compute = CTR_BF16 the copy is the bf16
  * (nearest-even) rounding of the fp32 pooled vectors, as the separate call rounds them.
  * table, dtype, total_rows, dim, row_base, num_tables, indices, index_type, nnz, offsets,
- * batch: as ctr_embbag_fwd.  Supported: dim / (values per 16 bytes) a power of two up to 32,
- * num_tables <= 256, one sample's pooled copy within 46 KiB (bf16 compute: F*(dim+8)*2 bytes,
- * fp32: F*(dim+1)*4); compute = CTR_BF16 needs dim in {16, 32, 64, 128} and F <= 128.  Other
- * shapes return CTR_ERR_UNSUPPORTED (the two separate calls cover them).  Z and R must not
- * overlap the table, indices or offsets.
+ * batch: as ctr_embbag_fwd, except that CTR_F16 tables are not taken (CTR_ERR_UNSUPPORTED:
+ * the two separate calls cover them).  Supported: dim / (values per 16 bytes) a power of two
+ * up to 32, num_tables <= 256, one sample's pooled copy within 46 KiB (bf16 compute:
+ * F*(dim+8)*2 bytes, fp32: F*(dim+1)*4); compute = CTR_BF16 needs dim in {16, 32, 64, 128}
+ * and F <= 128.  Other shapes return CTR_ERR_UNSUPPORTED (the two separate calls cover them).
+ * Z and R must not overlap the table, indices or offsets.
  */
 int32_t ctr_embbag_interaction_fwd(const void* table, int32_t dtype, int64_t total_rows,
                                    int32_t dim, const int64_t* row_base, int32_t num_tables,
@@ -318,7 +327,7 @@ int32_t ctr_fm_interaction_bwd(const float* Z, const float* dout, int64_t batch,
  * ctr_init_tables_hash -- fills a table with the counter-based values used by the seeded
  * workloads (input preparation, not part of the method): element (r, c) of table t is
  * x = fp32(2u - 1) * fp32(1/sqrt(rows_t)) with u = (splitmix64 output from state
- * seed ^ (r*dim + c)) >> 40, times 2^-24, stored as fp32 or bf16 nearest-even.
+ * seed ^ (r*dim + c)) >> 40, times 2^-24, stored as fp32, or bf16 or fp16 nearest-even.
  * row_base_host: host int64 [num_tables + 1].
  */
 int32_t ctr_init_tables_hash(void* table, int32_t dtype, int32_t dim,

@@ -38,13 +38,17 @@ int bitlen(uint64_t x) {
   return b;
 }
 
+// The kernels' element-type codes are the table dtype codes.
+static_assert(ctr::kEltF32 == CTR_F32 && ctr::kEltBF16 == CTR_BF16 && ctr::kEltF16 == CTR_F16,
+              "table element codes");
+
 int32_t check_table(const void* table, int32_t dtype, int64_t total_rows, int32_t dim) {
   if (!table) return fail(CTR_ERR_INVALID_ARGUMENT, "table is NULL");
-  if (dtype != CTR_F32 && dtype != CTR_BF16)
-    return fail(CTR_ERR_INVALID_ARGUMENT, "dtype %d is not CTR_F32 or CTR_BF16", dtype);
+  if (dtype != CTR_F32 && dtype != CTR_BF16 && dtype != CTR_F16)
+    return fail(CTR_ERR_INVALID_ARGUMENT, "dtype %d is not CTR_F32, CTR_BF16 or CTR_F16", dtype);
   if (total_rows < 0) return fail(CTR_ERR_INVALID_ARGUMENT, "total_rows < 0");
   if (dim <= 0) return fail(CTR_ERR_INVALID_ARGUMENT, "dim must be positive");
-  const int e = dtype == CTR_BF16 ? 8 : 4;
+  const int e = dtype != CTR_F32 ? 8 : 4;
   if (dim % e != 0)
     return fail(CTR_ERR_UNSUPPORTED, "dim %d is not a multiple of the 16-byte vector (%d)", dim, e);
   if (dim / e > 256) return fail(CTR_ERR_UNSUPPORTED, "dim %d above the 4 KiB row limit", dim);
@@ -169,7 +173,7 @@ int32_t ctr_gather_rows(const void* table, int32_t dtype, int64_t total_rows, in
   if (capacity > 0 && (!rows || !num_rows || !out))
     return fail(CTR_ERR_INVALID_ARGUMENT, "rows, num_rows and out are required");
   if (out && !aligned16(out)) return fail(CTR_ERR_UNSUPPORTED, "out is not 16-byte aligned");
-  return hip_status(ctr::launch_gather_rows(table, dtype == CTR_BF16, total_rows, dim, rows,
+  return hip_status(ctr::launch_gather_rows(table, dtype, total_rows, dim, rows,
                                             num_rows, capacity, out, (hipStream_t)stream),
                     "ctr_gather_rows");
 }
@@ -195,7 +199,7 @@ int32_t ctr_embbag_fwd(const void* table, int32_t dtype, int64_t total_rows, int
     return fail(CTR_ERR_INVALID_ARGUMENT, "output strides smaller than dim");
   if (!aligned16(out) || out_stride_b % 4 || out_stride_t % 4)
     return fail(CTR_ERR_UNSUPPORTED, "out must be 16-byte aligned with strides multiple of 4");
-  return hip_status(ctr::launch_embbag_fwd(table, dtype == CTR_BF16, total_rows, dim, row_base,
+  return hip_status(ctr::launch_embbag_fwd(table, dtype, total_rows, dim, row_base,
                                            num_tables, indices, index_type == CTR_I64, nnz,
                                            offsets, batch, out, out_stride_b, out_stride_t,
                                            (hipStream_t)stream),
@@ -267,8 +271,8 @@ static int32_t embbag_bwd_sgd_common(const void* grad, bool grad_bf16, int64_t g
     if (dim % 4) return fail(CTR_ERR_UNSUPPORTED, "dim %d is not a multiple of 4", dim);
     if (stochastic) return fail(CTR_ERR_INVALID_ARGUMENT, "stochastic rounding needs a table");
   }
-  if (stochastic && dtype != CTR_BF16)
-    return fail(CTR_ERR_UNSUPPORTED, "stochastic rounding needs a CTR_BF16 table");
+  if (stochastic && dtype == CTR_F32)
+    return fail(CTR_ERR_UNSUPPORTED, "stochastic rounding needs a CTR_BF16 or CTR_F16 table");
   if (dim > 1024) return fail(CTR_ERR_UNSUPPORTED, "dim %d above 1024", dim);
   if (nnz < 0 || nnz > kMaxElems) return fail(CTR_ERR_INVALID_ARGUMENT, "bad nnz");
   if (num_tables < 1) return fail(CTR_ERR_INVALID_ARGUMENT, "num_tables must be >= 1");
@@ -311,7 +315,10 @@ static int32_t embbag_bwd_sgd_common(const void* grad, bool grad_bf16, int64_t g
     return fail(CTR_ERR_UNSUPPORTED, "sorted_src is not 16-byte aligned");
   if (!noalloc && !aligned16(workspace))
     return fail(CTR_ERR_UNSUPPORTED, "workspace is not 16-byte aligned");
-  const int mode = !table ? 0 : dtype == CTR_BF16 ? (stochastic ? 3 : 2) : 1;
+  const int mode = !table               ? 0
+                   : dtype == CTR_BF16 ? (stochastic ? 3 : 2)
+                   : dtype == CTR_F16  ? (stochastic ? 5 : 4)
+                                       : 1;
   if (noalloc)
     return hip_status(ctr::launch_embbag_bwd_noalloc(
                           grad, grad_bf16, grad_stride_b, grad_stride_t, offsets, batch,
@@ -417,15 +424,15 @@ static int32_t sparse_sgd_common(void* table, int32_t dtype, int64_t total_rows,
   g_msg[0] = 0;
   int32_t st = check_table(table, dtype, total_rows, dim);
   if (st) return st;
-  if (stochastic && dtype != CTR_BF16)
-    return fail(CTR_ERR_UNSUPPORTED, "stochastic rounding needs a CTR_BF16 table");
+  if (stochastic && dtype == CTR_F32)
+    return fail(CTR_ERR_UNSUPPORTED, "stochastic rounding needs a CTR_BF16 or CTR_F16 table");
   if (capacity < 0 || capacity > kMaxElems) return fail(CTR_ERR_INVALID_ARGUMENT, "bad capacity");
   if (capacity > 0 && (!uniq || !num_unique || !row_grads))
     return fail(CTR_ERR_INVALID_ARGUMENT, "uniq, num_unique and row_grads are required");
   if (!std::isfinite(lr)) return fail(CTR_ERR_INVALID_ARGUMENT, "lr is not finite");
   if (row_grads && !aligned16(row_grads))
     return fail(CTR_ERR_UNSUPPORTED, "row_grads is not 16-byte aligned");
-  return hip_status(ctr::launch_sparse_sgd(table, dtype == CTR_BF16, total_rows, dim, uniq,
+  return hip_status(ctr::launch_sparse_sgd(table, dtype, total_rows, dim, uniq,
                                            num_unique, capacity, row_grads, lr, stochastic, seed,
                                            (hipStream_t)stream),
                     name);
@@ -516,6 +523,9 @@ int32_t ctr_embbag_interaction_fwd(const void* table, int32_t dtype, int64_t tot
   g_msg[0] = 0;
   int32_t st = check_table(table, dtype, total_rows, dim);
   if (st) return st;
+  if (dtype == CTR_F16)
+    return fail(CTR_ERR_UNSUPPORTED,
+                "CTR_F16 tables: ctr_embbag_fwd then ctr_dot_interaction_fwd");
   if (index_type != CTR_I32 && index_type != CTR_I64)
     return fail(CTR_ERR_INVALID_ARGUMENT, "index_type %d is not CTR_I32 or CTR_I64", index_type);
   if (num_tables < 1) return fail(CTR_ERR_INVALID_ARGUMENT, "num_tables must be >= 1");
@@ -652,7 +662,7 @@ int32_t ctr_dict_embbag_fwd(const int64_t* values, int64_t nnz, const int64_t* o
               out_stride_t < 0))
     return fail(CTR_ERR_UNSUPPORTED, "out must be 16-byte aligned with strides multiple of 4");
   return hip_status(ctr::launch_dict_pool(values, nnz, offsets, batch, num_tables, hot_rows,
-                                          num_hot, table, num_rows, dtype == CTR_BF16, dim, out,
+                                          num_hot, table, num_rows, dtype, dim, out,
                                           out_stride_b, out_stride_t, (hipStream_t)stream),
                     "ctr_dict_embbag_fwd");
 }
@@ -671,7 +681,7 @@ int32_t ctr_init_tables_hash(void* table, int32_t dtype, int32_t dim, const int6
     const int64_t rows = row_base_host[t + 1] - row_base_host[t];
     if (rows == 0) continue;
     const float scale = (float)(1.0 / std::sqrt((double)rows));
-    hipError_t e = ctr::launch_init_table(table, dtype == CTR_BF16, dim, row_base_host[t], rows,
+    hipError_t e = ctr::launch_init_table(table, dtype, dim, row_base_host[t], rows,
                                           scale, seed, (hipStream_t)stream);
     if (e != hipSuccess) return hip_status(e, "ctr_init_tables_hash");
   }

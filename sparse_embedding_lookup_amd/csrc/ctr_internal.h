@@ -55,11 +55,80 @@ __device__ __forceinline__ uint32_t f32_to_bf16_sr(float x, uint32_t r) {
   return (b >> 16) + (r < (b & 0xFFFFu) ? 1u : 0u);
 }
 
-// Sixteen bytes of a row widened to fp32: 4 floats (fp32 rows) or 8 floats (bf16 rows).
-template <bool BF16>
+// ----------------------------------------------------------------------------- binary16
+// IEEE binary16 (1 sign, 5 exponent, 10 fraction bits; largest finite 65504, subnormal
+// quantum 2^-24).  Widening to binary32 is exact; the narrowing below is the hardware
+// conversion under the default round-to-nearest-even mode (overflow gives infinity,
+// subnormals are kept).
+__device__ __forceinline__ float f16_lo(uint32_t pair) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)(pair & 0xFFFFu));
+}
+__device__ __forceinline__ float f16_hi(uint32_t pair) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)(pair >> 16));
+}
+// The empty asm pins f as the binary32 value it is: without it the compiler may fold the
+// multiply or fused multiply-add that produced f into one mixed-precision instruction
+// (v_fma_mixlo_f16) that rounds the exact result to binary16 once, skipping the binary32
+// rounding the stored value is defined by.
+__device__ __forceinline__ uint32_t f32_to_f16_bits(float f) {
+  __asm__ volatile("" : "+v"(f));
+  return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)f);
+}
+
+// binary32 -> binary16 with stochastic rounding, the same rule as f32_to_bf16_sr: with lo
+// the binary16 value next to x toward zero and q the binary16 spacing there, round away from
+// zero iff r < 2^16 (|x| - |lo|) / q.  In the normal range 13 bits are dropped, so that
+// threshold is the dropped bits times 8; below 2^-14 the spacing is 2^-24 and the fraction
+// is taken in binary32 arithmetic, which is exact there.  |x| >= 2^16 (and infinity) gives
+// infinity, as does rounding up from the largest finite binade; NaN gives a quiet NaN.
+__device__ __forceinline__ uint32_t f32_to_f16_sr(float x, uint32_t r) {
+  const uint32_t b = __float_as_uint(x);
+  const uint32_t sign = (b >> 16) & 0x8000u;
+  const uint32_t a = b & 0x7FFFFFFFu;
+  if (a > 0x7F800000u) return 0x7E00u;
+  if (a >= 0x47800000u) return sign | 0x7C00u;
+  uint32_t h;
+  bool up;
+  if (a >= 0x38800000u) {                       // 2^-14 <= |x| < 2^16
+    const uint32_t m = a & 0x7FFFFFu;
+    h = (((a >> 23) - 112u) << 10) | (m >> 13);
+    up = r < ((m & 0x1FFFu) << 3);
+  } else {                                      // binary16 subnormals and zero
+    const float q = __uint_as_float(a) * 16777216.0f;    // |x| / 2^-24, exact
+    const float n = __builtin_truncf(q);
+    h = (uint32_t)n;
+    up = (float)r < (q - n) * 65536.0f;
+  }
+  return sign | (h + (up ? 1u : 0u));
+}
+
+// Stored element types of a table row: binary32, bfloat16 or binary16 (the two 16-bit types
+// hold 8 values per 16-byte vector, binary32 4).
+enum : int { kEltF32 = 0, kEltBF16 = 1, kEltF16 = 2 };
+
+template <int TY>
+__device__ __forceinline__ float half_lo(uint32_t pair) {
+  if constexpr (TY == kEltF16) return f16_lo(pair);
+  else return bf16_lo(pair);
+}
+template <int TY>
+__device__ __forceinline__ float half_hi(uint32_t pair) {
+  if constexpr (TY == kEltF16) return f16_hi(pair);
+  else return bf16_hi(pair);
+}
+// binary32 -> the 16-bit type, nearest-even (SR false) or stochastic with bits r (SR true).
+template <int TY, bool SR>
+__device__ __forceinline__ uint32_t to_half(float f, uint32_t r) {
+  if constexpr (TY == kEltF16) return SR ? f32_to_f16_sr(f, r) : f32_to_f16_bits(f);
+  else return SR ? f32_to_bf16_sr(f, r) : f32_to_bf16_bits(f);
+}
+
+// Sixteen bytes of a row widened to fp32: 4 floats (binary32 rows) or 8 floats (16-bit rows).
+// TY is a kElt code (a bool selects binary32 or bfloat16).
+template <int TY>
 struct Vec;
 template <>
-struct Vec<false> {
+struct Vec<kEltF32> {
   static constexpr int kElems = 4;
   float v[4];
   __device__ __forceinline__ void zero() { v[0] = v[1] = v[2] = v[3] = 0.f; }
@@ -69,8 +138,9 @@ struct Vec<false> {
     v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w;
   }
 };
-template <>
-struct Vec<true> {
+template <int TY>
+struct Vec {
+  static_assert(TY == kEltBF16 || TY == kEltF16, "a 16-bit element type");
   static constexpr int kElems = 8;
   float v[8];
   __device__ __forceinline__ void zero() {
@@ -83,10 +153,10 @@ struct Vec<true> {
   }
   __device__ __forceinline__ void load(const void* p) {
     uint4 x = *reinterpret_cast<const uint4*>(p);
-    v[0] = bf16_lo(x.x); v[1] = bf16_hi(x.x);
-    v[2] = bf16_lo(x.y); v[3] = bf16_hi(x.y);
-    v[4] = bf16_lo(x.z); v[5] = bf16_hi(x.z);
-    v[6] = bf16_lo(x.w); v[7] = bf16_hi(x.w);
+    v[0] = half_lo<TY>(x.x); v[1] = half_hi<TY>(x.x);
+    v[2] = half_lo<TY>(x.y); v[3] = half_hi<TY>(x.y);
+    v[4] = half_lo<TY>(x.z); v[5] = half_hi<TY>(x.z);
+    v[6] = half_lo<TY>(x.w); v[7] = half_hi<TY>(x.w);
   }
 };
 

@@ -22,19 +22,19 @@ hipError_t launch_unique(const void* ids, bool ids64, int64_t n, const int64_t* 
                          int32_t* seg_offsets, int4* sorted_src, void* workspace,
                          hipStream_t s);
 
-// embbag.hip
-hipError_t launch_embbag_fwd(const void* table, bool bf16, int64_t total_rows, int dim,
+// embbag.hip (elt: the table's kElt code, ctr_internal.h)
+hipError_t launch_embbag_fwd(const void* table, int elt, int64_t total_rows, int dim,
                              const int64_t* row_base, int32_t num_tables, const void* idx,
                              bool idx64, int64_t nnz, const int64_t* offsets, int64_t batch,
                              float* out, int64_t sb, int64_t st, hipStream_t s);
-hipError_t launch_gather_rows(const void* table, bool bf16, int64_t total_rows, int dim,
+hipError_t launch_gather_rows(const void* table, int elt, int64_t total_rows, int dim,
                               const int64_t* rows, const int32_t* num_rows, int64_t capacity,
                               float* out, hipStream_t s);
-hipError_t launch_sparse_sgd(void* table, bool bf16, int64_t total_rows, int dim,
+hipError_t launch_sparse_sgd(void* table, int elt, int64_t total_rows, int dim,
                              const int64_t* uniq, const int32_t* num_unique, int64_t capacity,
                              const float* g, float lr, bool stochastic, uint64_t seed,
                              hipStream_t s);
-hipError_t launch_init_table(void* table, bool bf16, int dim, int64_t row_begin,
+hipError_t launch_init_table(void* table, int elt, int dim, int64_t row_begin,
                              int64_t rows, float scale, uint64_t seed, hipStream_t s);
 hipError_t launch_validate_csr(const void* idx, bool idx64, int64_t nnz, const int64_t* offsets,
                                int64_t batch, int32_t num_tables, const int64_t* row_base,
@@ -80,7 +80,7 @@ hipError_t launch_dict_lookup(const int64_t* ids, int64_t n, const void* slots,
                               int64_t capacity, int64_t* values, hipStream_t s);
 hipError_t launch_dict_pool(const int64_t* values, int64_t nnz, const int64_t* offsets,
                             int64_t batch, int32_t num_tables, const void* hot,
-                            int64_t hot_rows, const void* cold, int64_t cold_rows, bool bf16,
+                            int64_t hot_rows, const void* cold, int64_t cold_rows, int elt,
                             int dim, float* out, int64_t sb, int64_t st, hipStream_t s);
 
 // interaction.hip

@@ -107,13 +107,13 @@ __global__ __launch_bounds__(kThreads) void dict_lookup_kernel(const int64_t* __
 // nothing.  The dictionary table has at least one row.  A group of G lanes owns one bag and
 // keeps kU row loads in flight (kU = 1 when the bags average one ID, so that no load is
 // spent on a bag's missing occurrences); rows are added in occurrence order.
-template <bool BF16, int G, int VPL, int kU>
+template <int TY, int G, int VPL, int kU>
 __global__ __launch_bounds__(kThreads) void dict_pool_kernel(
     const int64_t* __restrict__ values, int64_t nnz, const int64_t* __restrict__ offsets,
     int64_t batch, int64_t num_bags, const char* __restrict__ hot, int64_t hot_rows,
     const char* __restrict__ cold, int64_t cold_rows, int64_t row_bytes, int vecs,
     float* __restrict__ out, int64_t sb, int64_t st) {
-  constexpr int E = BF16 ? 8 : 4;
+  constexpr int E = TY != kEltF32 ? 8 : 4;
   const int lane = threadIdx.x & (G - 1);
   const int64_t bag = (int64_t)blockIdx.x * (kThreads / G) + threadIdx.x / G;
   if (bag >= num_bags) return;
@@ -158,11 +158,11 @@ __global__ __launch_bounds__(kThreads) void dict_pool_kernel(
       if (k0 + u >= o1) break;
 #pragma unroll
       for (int a = 0; a < VPL; ++a) {
-        if (BF16) {
-          acc[a][0] += bf16_lo(rv[u][a].x); acc[a][1] += bf16_hi(rv[u][a].x);
-          acc[a][2] += bf16_lo(rv[u][a].y); acc[a][3] += bf16_hi(rv[u][a].y);
-          acc[a][4 % E] += bf16_lo(rv[u][a].z); acc[a][5 % E] += bf16_hi(rv[u][a].z);
-          acc[a][6 % E] += bf16_lo(rv[u][a].w); acc[a][7 % E] += bf16_hi(rv[u][a].w);
+        if constexpr (TY != kEltF32) {
+          acc[a][0] += half_lo<TY>(rv[u][a].x); acc[a][1] += half_hi<TY>(rv[u][a].x);
+          acc[a][2] += half_lo<TY>(rv[u][a].y); acc[a][3] += half_hi<TY>(rv[u][a].y);
+          acc[a][4 % E] += half_lo<TY>(rv[u][a].z); acc[a][5 % E] += half_hi<TY>(rv[u][a].z);
+          acc[a][6 % E] += half_lo<TY>(rv[u][a].w); acc[a][7 % E] += half_hi<TY>(rv[u][a].w);
         } else {
           acc[a][0] += __uint_as_float(rv[u][a].x); acc[a][1] += __uint_as_float(rv[u][a].y);
           acc[a][2] += __uint_as_float(rv[u][a].z); acc[a][3] += __uint_as_float(rv[u][a].w);
@@ -208,26 +208,30 @@ hipError_t launch_dict_lookup(const int64_t* ids, int64_t n, const void* slots,
 
 hipError_t launch_dict_pool(const int64_t* values, int64_t nnz, const int64_t* offsets,
                             int64_t batch, int32_t num_tables, const void* hot,
-                            int64_t hot_rows, const void* cold, int64_t cold_rows, bool bf16,
+                            int64_t hot_rows, const void* cold, int64_t cold_rows, int elt,
                             int dim, float* out, int64_t sb, int64_t st, hipStream_t s) {
   const int64_t num_bags = (int64_t)num_tables * batch;
   if (num_bags == 0) return hipSuccess;
-  const int E = bf16 ? 8 : 4;
+  const int E = elt != kEltF32 ? 8 : 4;
   const int vecs = dim / E;
   const RowGeom rg = row_geom(vecs);
-  const int64_t row_bytes = (int64_t)dim * (bf16 ? 2 : 4);
+  const int64_t row_bytes = (int64_t)dim * (elt != kEltF32 ? 2 : 4);
   const char* hb = static_cast<const char*>(hot);
   const char* cb = static_cast<const char*>(cold);
   const bool single = nnz <= num_bags + num_bags / 2;     // about one ID per bag
 #define CTR_DICT_POOL_U(G_, VPL_, U_)                                                    \
   do {                                                                                   \
     const int64_t blocks = (num_bags + (kThreads / (G_)) - 1) / (kThreads / (G_));       \
-    if (bf16)                                                                            \
-      dict_pool_kernel<true, G_, VPL_, U_><<<(unsigned)blocks, kThreads, 0, s>>>(        \
+    if (elt == kEltF16)                                                                  \
+      dict_pool_kernel<kEltF16, G_, VPL_, U_><<<(unsigned)blocks, kThreads, 0, s>>>(     \
+          values, nnz, offsets, batch, num_bags, hb, hot_rows, cb, cold_rows, row_bytes, \
+          vecs, out, sb, st);                                                            \
+    else if (elt == kEltBF16)                                                            \
+      dict_pool_kernel<kEltBF16, G_, VPL_, U_><<<(unsigned)blocks, kThreads, 0, s>>>(    \
           values, nnz, offsets, batch, num_bags, hb, hot_rows, cb, cold_rows, row_bytes, \
           vecs, out, sb, st);                                                            \
     else                                                                                 \
-      dict_pool_kernel<false, G_, VPL_, U_><<<(unsigned)blocks, kThreads, 0, s>>>(       \
+      dict_pool_kernel<kEltF32, G_, VPL_, U_><<<(unsigned)blocks, kThreads, 0, s>>>(     \
           values, nnz, offsets, batch, num_bags, hb, hot_rows, cb, cold_rows, row_bytes, \
           vecs, out, sb, st);                                                            \
   } while (0)

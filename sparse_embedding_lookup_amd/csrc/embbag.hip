@@ -1,12 +1,12 @@
 // embbag.hip -- row gathers on gfx950: sum-pooled embedding bags, the batch-sized matrix
 // fetch, the sparse SGD row update, the counter-based table fill and a CSR checker.
 //
-// Layout of the work: a row of the table is `vecs` 16-byte vectors (fp32: 4 values, bf16:
-// 8 values).  A group of G lanes (G a power of two, at most 64) reads one row at a time; each
-// lane loads VPL vectors per row with 128-bit loads, so a wavefront gathers 64/G rows per
-// load instruction, and a group keeps kU row loads in flight.  Pooling splits a block's
-// bag-aligned occurrence range evenly over its groups (bags cut at group edges are joined in
-// LDS), so a long or heavy-tailed bag length does not set the kernel's tail.
+// Layout of the work: a row of the table is `vecs` 16-byte vectors (fp32: 4 values, bf16 or
+// fp16: 8 values).  A group of G lanes (G a power of two, at most 64) reads one row at a
+// time; each lane loads VPL vectors per row with 128-bit loads, so a wavefront gathers 64/G
+// rows per load instruction, and a group keeps kU row loads in flight.  Pooling splits a
+// block's bag-aligned occurrence range evenly over its groups (bags cut at group edges are
+// joined in LDS), so a long or heavy-tailed bag length does not set the kernel's tail.
 //
 // Pooling: "DHEN" notes, 2.1 "Feature Processing Layer" (one d-dim vector per sparse
 // feature; sum pooling is the reading taken).  Fetch into the batch-sized matrix and the
@@ -20,14 +20,15 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kUnroll = 8;
 
-// Raw 16 bytes of a row (4 fp32 or 8 bf16), widened only when accumulated.
-template <bool BF16>
+// Raw 16 bytes of a row (4 binary32 or 8 bfloat16 / binary16 values, TY a kElt code),
+// widened only when accumulated.
+template <int TY>
 __device__ __forceinline__ void accumulate(float* acc, const uint4& x) {
-  if (BF16) {
-    acc[0] += bf16_lo(x.x); acc[1] += bf16_hi(x.x);
-    acc[2] += bf16_lo(x.y); acc[3] += bf16_hi(x.y);
-    acc[4] += bf16_lo(x.z); acc[5] += bf16_hi(x.z);
-    acc[6] += bf16_lo(x.w); acc[7] += bf16_hi(x.w);
+  if constexpr (TY != kEltF32) {
+    acc[0] += half_lo<TY>(x.x); acc[1] += half_hi<TY>(x.x);
+    acc[2] += half_lo<TY>(x.y); acc[3] += half_hi<TY>(x.y);
+    acc[4] += half_lo<TY>(x.z); acc[5] += half_hi<TY>(x.z);
+    acc[6] += half_lo<TY>(x.w); acc[7] += half_hi<TY>(x.w);
   } else {
     acc[0] += __uint_as_float(x.x); acc[1] += __uint_as_float(x.y);
     acc[2] += __uint_as_float(x.z); acc[3] += __uint_as_float(x.w);
@@ -40,13 +41,13 @@ constexpr int kMaxBagsPerGroup = 16;
 // their occurrences are walked in order in chunks of kU (indices loaded cooperatively and
 // broadcast by shuffles, kU row loads in flight), and a bag's sum is stored when the walk
 // passes its end.  Rows of a bag are added in occurrence order.
-template <typename TIdx, bool BF16, int G, int VPL>
+template <typename TIdx, int TY, int G, int VPL>
 __global__ __launch_bounds__(kThreads) void embbag_fwd_kernel(
     const char* __restrict__ table, int64_t total_rows, int64_t row_bytes, int vecs,
     const int64_t* __restrict__ row_base, const TIdx* __restrict__ idx, int64_t nnz,
     const int64_t* __restrict__ offsets, int64_t batch, int64_t num_bags, int nbg,
     float* __restrict__ out, int64_t sb, int64_t st) {
-  constexpr int E = BF16 ? 8 : 4;
+  constexpr int E = TY != kEltF32 ? 8 : 4;
   constexpr int kGroups = kThreads / G;
   constexpr int kU = (VPL == 1 && G <= 8) ? 16 : 8;   // rows in flight per group
   constexpr int kRegs = (kU + G - 1) / G;
@@ -123,7 +124,7 @@ __global__ __launch_bounds__(kThreads) void embbag_fwd_kernel(
       if (k0 + u >= o_end) break;
       while (cur < bagu[u]) flush(cur++);
 #pragma unroll
-      for (int a = 0; a < VPL; ++a) accumulate<BF16>(acc[a], rv[u][a]);
+      for (int a = 0; a < VPL; ++a) accumulate<TY>(acc[a], rv[u][a]);
     }
   }
   while (cur < nb) flush(cur++);
@@ -145,13 +146,13 @@ constexpr double kPoolRows = 128.0;
 constexpr int64_t kPoolMinBlocks = 2048;
 constexpr double kPoolMinRows = 20.0;
 
-template <typename TIdx, bool BF16, int G, int VPL>
+template <typename TIdx, int TY, int G, int VPL>
 __global__ __launch_bounds__(kThreads) void embbag_fwd_balanced_kernel(
     const char* __restrict__ table, int64_t total_rows, int64_t row_bytes, int vecs,
     const int64_t* __restrict__ row_base, const TIdx* __restrict__ idx, int64_t nnz,
     const int64_t* __restrict__ offsets, int64_t batch, int64_t num_bags, int nbb,
     float* __restrict__ out, int64_t sb, int64_t st) {
-  constexpr int E = BF16 ? 8 : 4;
+  constexpr int E = TY != kEltF32 ? 8 : 4;
   constexpr int kGroups = kThreads / G;
   constexpr int kU = (VPL == 1 && G <= 8) ? 16 : 8;   // rows in flight per group
   constexpr int kRegs = (kU + G - 1) / G;
@@ -269,7 +270,7 @@ __global__ __launch_bounds__(kThreads) void embbag_fwd_balanced_kernel(
           piece_at_start = true;               // a later bag begins inside the share
         }
 #pragma unroll
-        for (int a = 0; a < VPL; ++a) accumulate<BF16>(acc[a], rv[u][a]);
+        for (int a = 0; a < VPL; ++a) accumulate<TY>(acc[a], rv[u][a]);
       }
     }
     close_piece(q1 == s_off[c + 1]);
@@ -308,12 +309,12 @@ __global__ __launch_bounds__(kThreads) void embbag_fwd_balanced_kernel(
 }
 
 // E[u] = W[rows[u]] widened to fp32, u < min(num_rows, capacity).
-template <bool BF16, int G, int VPL>
+template <int TY, int G, int VPL>
 __global__ __launch_bounds__(kThreads) void gather_rows_kernel(
     const char* __restrict__ table, int64_t total_rows, int64_t row_bytes, int vecs,
     const int64_t* __restrict__ rows, const int32_t* __restrict__ num_rows, int64_t capacity,
     float* __restrict__ out, int64_t out_stride) {
-  using V = Vec<BF16>;
+  using V = Vec<TY>;
   constexpr int E = V::kElems;
   const int lane = threadIdx.x & (G - 1);
   const int64_t u = (int64_t)blockIdx.x * (kThreads / G) + threadIdx.x / G;
@@ -333,14 +334,15 @@ __global__ __launch_bounds__(kThreads) void gather_rows_kernel(
   }
 }
 
-// W[uniq[u]] = round(W[uniq[u]] - lr * g[u]) for u < min(num_unique, capacity); bf16 rounds
-// to nearest-even, or stochastically (SR) with the element's random bits from `seed`.
-template <bool BF16, bool SR, int G, int VPL>
+// W[uniq[u]] = round(W[uniq[u]] - lr * g[u]) for u < min(num_unique, capacity); a 16-bit
+// table (bfloat16 or binary16) rounds to nearest-even, or stochastically (SR) with the
+// element's random bits from `seed`.
+template <int TY, bool SR, int G, int VPL>
 __global__ __launch_bounds__(kThreads) void sparse_sgd_kernel(
     char* __restrict__ table, int64_t total_rows, int64_t row_bytes, int vecs,
     const int64_t* __restrict__ uniq, const int32_t* __restrict__ num_unique, int64_t capacity,
     const float* __restrict__ g, int64_t g_stride, float lr, uint64_t seed) {
-  using V = Vec<BF16>;
+  using V = Vec<TY>;
   constexpr int E = V::kElems;
   const int lane = threadIdx.x & (G - 1);
   const int64_t u = (int64_t)blockIdx.x * (kThreads / G) + threadIdx.x / G;
@@ -368,7 +370,7 @@ __global__ __launch_bounds__(kThreads) void sparse_sgd_kernel(
     float nw[E];
 #pragma unroll
     for (int e = 0; e < E; ++e) nw[e] = __builtin_fmaf(-lr, gr[e], w.v[e]);
-    if (BF16) {
+    if constexpr (TY != kEltF32) {
       uint32_t h[E];
       uint64_t bits[2] = {0, 0};
       if (SR) {
@@ -376,8 +378,7 @@ __global__ __launch_bounds__(kThreads) void sparse_sgd_kernel(
         bits[1] = sr_bits4(seed, key, (int64_t)vi * E + 4, vecs * E);
       }
 #pragma unroll
-      for (int e = 0; e < E; ++e)
-        h[e] = SR ? f32_to_bf16_sr(nw[e], sr_take(bits[e / 4], e % 4)) : f32_to_bf16_bits(nw[e]);
+      for (int e = 0; e < E; ++e) h[e] = to_half<TY, SR>(nw[e], sr_take(bits[e / 4], e % 4));
       uint4 q;
       q.x = h[0] | (h[1] << 16);
       q.y = h[2] | (h[3] << 16);
@@ -400,11 +401,11 @@ __device__ __forceinline__ float hash_value(uint64_t seed, int64_t r, int64_t c,
   return __fmul_rn(sgn, scale);
 }
 
-template <bool BF16>
+template <int TY>
 __global__ __launch_bounds__(kThreads) void init_table_kernel(char* __restrict__ table, int dim,
                                                               int64_t row_begin, int64_t rows,
                                                               float scale, uint64_t seed) {
-  constexpr int E = BF16 ? 8 : 4;
+  constexpr int E = TY != kEltF32 ? 8 : 4;
   const int64_t vecs = dim / E;
   const int64_t total = rows * vecs;
   const int64_t stride = (int64_t)gridDim.x * kThreads;
@@ -414,13 +415,14 @@ __global__ __launch_bounds__(kThreads) void init_table_kernel(char* __restrict__
     float x[E];
 #pragma unroll
     for (int e = 0; e < E; ++e) x[e] = hash_value(seed, r, c0 + e, dim, scale);
-    char* p = table + (r * dim + c0) * (BF16 ? 2 : 4);
-    if (BF16) {
+    char* p = table + (r * dim + c0) * (TY != kEltF32 ? 2 : 4);
+    if constexpr (TY != kEltF32) {
+      auto h = [](float f) { return to_half<TY, false>(f, 0u); };
       uint4 w;
-      w.x = f32_to_bf16_bits(x[0]) | (f32_to_bf16_bits(x[1]) << 16);
-      w.y = f32_to_bf16_bits(x[2]) | (f32_to_bf16_bits(x[3]) << 16);
-      w.z = f32_to_bf16_bits(x[4 % E]) | (f32_to_bf16_bits(x[5 % E]) << 16);
-      w.w = f32_to_bf16_bits(x[6 % E]) | (f32_to_bf16_bits(x[7 % E]) << 16);
+      w.x = h(x[0]) | (h(x[1]) << 16);
+      w.y = h(x[2]) | (h(x[3]) << 16);
+      w.z = h(x[4 % E]) | (h(x[5 % E]) << 16);
+      w.w = h(x[6 % E]) | (h(x[7 % E]) << 16);
       *reinterpret_cast<uint4*>(p) = w;
     } else {
       *reinterpret_cast<float4*>(p) = make_float4(x[0], x[1], x[2], x[3]);
@@ -475,39 +477,38 @@ __global__ __launch_bounds__(kThreads) void validate_csr_kernel(
     }                                                                       \
   } while (0)
 
-hipError_t launch_embbag_fwd(const void* table, bool bf16, int64_t total_rows, int dim,
+// Runs BODY with TY the kElt code `elt` as a compile-time constant.
+#define CTR_DISPATCH_ELT(elt, ...)                                          \
+  do {                                                                      \
+    if ((elt) == kEltF16) { constexpr int TY = kEltF16; __VA_ARGS__; }      \
+    else if ((elt) == kEltBF16) { constexpr int TY = kEltBF16; __VA_ARGS__; } \
+    else { constexpr int TY = kEltF32; __VA_ARGS__; }                       \
+  } while (0)
+
+hipError_t launch_embbag_fwd(const void* table, int elt, int64_t total_rows, int dim,
                              const int64_t* row_base, int32_t num_tables, const void* idx,
                              bool idx64, int64_t nnz, const int64_t* offsets, int64_t batch,
                              float* out, int64_t sb, int64_t st, hipStream_t s) {
-  const int E = bf16 ? 8 : 4;
+  const int E = elt != kEltF32 ? 8 : 4;
   const int vecs = dim / E;
   const RowGeom rg = row_geom(vecs);
-  const int64_t row_bytes = (int64_t)dim * (bf16 ? 2 : 4);
+  const int64_t row_bytes = (int64_t)dim * (elt != kEltF32 ? 2 : 4);
   const int64_t num_bags = (int64_t)num_tables * batch;
   if (num_bags == 0) return hipSuccess;
   const char* tb = static_cast<const char*>(table);
   const double avg = (double)nnz / (double)num_bags;
 #define CTR_FWD_LAUNCH(KERNEL, BLOCKS, PER)                                                    \
   do {                                                                                        \
-    if (bf16) {                                                                               \
+    CTR_DISPATCH_ELT(elt, {                                                                   \
       if (idx64)                                                                              \
-        KERNEL<int64_t, true, G, VPL><<<(unsigned)(BLOCKS), kThreads, 0, s>>>(                \
+        KERNEL<int64_t, TY, G, VPL><<<(unsigned)(BLOCKS), kThreads, 0, s>>>(                  \
             tb, total_rows, row_bytes, vecs, row_base, (const int64_t*)idx, nnz, offsets,     \
             batch, num_bags, PER, out, sb, st);                                               \
       else                                                                                    \
-        KERNEL<int32_t, true, G, VPL><<<(unsigned)(BLOCKS), kThreads, 0, s>>>(                \
+        KERNEL<int32_t, TY, G, VPL><<<(unsigned)(BLOCKS), kThreads, 0, s>>>(                  \
             tb, total_rows, row_bytes, vecs, row_base, (const int32_t*)idx, nnz, offsets,     \
             batch, num_bags, PER, out, sb, st);                                               \
-    } else {                                                                                  \
-      if (idx64)                                                                              \
-        KERNEL<int64_t, false, G, VPL><<<(unsigned)(BLOCKS), kThreads, 0, s>>>(               \
-            tb, total_rows, row_bytes, vecs, row_base, (const int64_t*)idx, nnz, offsets,     \
-            batch, num_bags, PER, out, sb, st);                                               \
-      else                                                                                    \
-        KERNEL<int32_t, false, G, VPL><<<(unsigned)(BLOCKS), kThreads, 0, s>>>(               \
-            tb, total_rows, row_bytes, vecs, row_base, (const int32_t*)idx, nnz, offsets,     \
-            batch, num_bags, PER, out, sb, st);                                               \
-    }                                                                                         \
+    });                                                                                       \
   } while (0)
   CTR_DISPATCH_G_VPL(rg.G, rg.VPL, {
     constexpr int kGroups = kThreads / G;
@@ -538,65 +539,64 @@ hipError_t launch_embbag_fwd(const void* table, bool bf16, int64_t total_rows, i
   return hipGetLastError();
 }
 
-hipError_t launch_gather_rows(const void* table, bool bf16, int64_t total_rows, int dim,
+hipError_t launch_gather_rows(const void* table, int elt, int64_t total_rows, int dim,
                               const int64_t* rows, const int32_t* num_rows, int64_t capacity,
                               float* out, hipStream_t s) {
   if (capacity == 0) return hipSuccess;
-  const int E = bf16 ? 8 : 4;
+  const int E = elt != kEltF32 ? 8 : 4;
   const int vecs = dim / E;
   const RowGeom rg = row_geom(vecs);
-  const int64_t row_bytes = (int64_t)dim * (bf16 ? 2 : 4);
+  const int64_t row_bytes = (int64_t)dim * (elt != kEltF32 ? 2 : 4);
   const char* tb = static_cast<const char*>(table);
   CTR_DISPATCH_G_VPL(rg.G, rg.VPL, {
     const int64_t blocks = (capacity + (kThreads / G) - 1) / (kThreads / G);
-    if (bf16)
-      gather_rows_kernel<true, G, VPL><<<(unsigned)blocks, kThreads, 0, s>>>(
-          tb, total_rows, row_bytes, vecs, rows, num_rows, capacity, out, dim);
-    else
-      gather_rows_kernel<false, G, VPL><<<(unsigned)blocks, kThreads, 0, s>>>(
-          tb, total_rows, row_bytes, vecs, rows, num_rows, capacity, out, dim);
+    CTR_DISPATCH_ELT(elt, gather_rows_kernel<TY, G, VPL><<<(unsigned)blocks, kThreads, 0, s>>>(
+                              tb, total_rows, row_bytes, vecs, rows, num_rows, capacity, out,
+                              dim));
   });
   return hipGetLastError();
 }
 
-hipError_t launch_sparse_sgd(void* table, bool bf16, int64_t total_rows, int dim,
+hipError_t launch_sparse_sgd(void* table, int elt, int64_t total_rows, int dim,
                              const int64_t* uniq, const int32_t* num_unique, int64_t capacity,
                              const float* g, float lr, bool stochastic, uint64_t seed,
                              hipStream_t s) {
   if (capacity == 0) return hipSuccess;
-  const int E = bf16 ? 8 : 4;
+  const int E = elt != kEltF32 ? 8 : 4;
   const int vecs = dim / E;
   const RowGeom rg = row_geom(vecs);
-  const int64_t row_bytes = (int64_t)dim * (bf16 ? 2 : 4);
+  const int64_t row_bytes = (int64_t)dim * (elt != kEltF32 ? 2 : 4);
   char* tb = static_cast<char*>(table);
   CTR_DISPATCH_G_VPL(rg.G, rg.VPL, {
     const int64_t blocks = (capacity + (kThreads / G) - 1) / (kThreads / G);
-    if (bf16 && stochastic)
-      sparse_sgd_kernel<true, true, G, VPL><<<(unsigned)blocks, kThreads, 0, s>>>(
+    if (elt == kEltF16 && stochastic)
+      sparse_sgd_kernel<kEltF16, true, G, VPL><<<(unsigned)blocks, kThreads, 0, s>>>(
           tb, total_rows, row_bytes, vecs, uniq, num_unique, capacity, g, dim, lr, seed);
-    else if (bf16)
-      sparse_sgd_kernel<true, false, G, VPL><<<(unsigned)blocks, kThreads, 0, s>>>(
+    else if (elt == kEltF16)
+      sparse_sgd_kernel<kEltF16, false, G, VPL><<<(unsigned)blocks, kThreads, 0, s>>>(
+          tb, total_rows, row_bytes, vecs, uniq, num_unique, capacity, g, dim, lr, seed);
+    else if (elt == kEltBF16 && stochastic)
+      sparse_sgd_kernel<kEltBF16, true, G, VPL><<<(unsigned)blocks, kThreads, 0, s>>>(
+          tb, total_rows, row_bytes, vecs, uniq, num_unique, capacity, g, dim, lr, seed);
+    else if (elt == kEltBF16)
+      sparse_sgd_kernel<kEltBF16, false, G, VPL><<<(unsigned)blocks, kThreads, 0, s>>>(
           tb, total_rows, row_bytes, vecs, uniq, num_unique, capacity, g, dim, lr, seed);
     else
-      sparse_sgd_kernel<false, false, G, VPL><<<(unsigned)blocks, kThreads, 0, s>>>(
+      sparse_sgd_kernel<kEltF32, false, G, VPL><<<(unsigned)blocks, kThreads, 0, s>>>(
           tb, total_rows, row_bytes, vecs, uniq, num_unique, capacity, g, dim, lr, seed);
   });
   return hipGetLastError();
 }
 
-hipError_t launch_init_table(void* table, bool bf16, int dim, int64_t row_begin, int64_t rows,
+hipError_t launch_init_table(void* table, int elt, int dim, int64_t row_begin, int64_t rows,
                              float scale, uint64_t seed, hipStream_t s) {
   if (rows == 0) return hipSuccess;
-  const int E = bf16 ? 8 : 4;
+  const int E = elt != kEltF32 ? 8 : 4;
   const int64_t total = rows * (dim / E);
   int64_t blocks = (total + kThreads - 1) / kThreads;
   if (blocks > 65536) blocks = 65536;
-  if (bf16)
-    init_table_kernel<true><<<(unsigned)blocks, kThreads, 0, s>>>(
-        static_cast<char*>(table), dim, row_begin, rows, scale, seed);
-  else
-    init_table_kernel<false><<<(unsigned)blocks, kThreads, 0, s>>>(
-        static_cast<char*>(table), dim, row_begin, rows, scale, seed);
+  CTR_DISPATCH_ELT(elt, init_table_kernel<TY><<<(unsigned)blocks, kThreads, 0, s>>>(
+                            static_cast<char*>(table), dim, row_begin, rows, scale, seed));
   return hipGetLastError();
 }
 

@@ -140,8 +140,9 @@ __device__ __forceinline__ int32_t key_after(const Src& S, int64_t q, int64_t n)
 }
 
 // Where a finished row gradient goes besides row_grads: nowhere (MODE 0), or straight into
-// the sparse SGD update W[uniq[u]] -= lr * g[u] of an fp32 (MODE 1) or bf16 table, rounded
-// to nearest-even (MODE 2) or stochastically with the element's bits from `seed` (MODE 3),
+// the sparse SGD update W[uniq[u]] -= lr * g[u] of an fp32 (MODE 1), bf16 or fp16 table,
+// rounded to nearest-even (MODE 2 bf16, 4 fp16) or stochastically with the element's bits
+// from `seed` (MODE 3 bf16, 5 fp16),
 // with the same arithmetic as the stand-alone update (one fused multiply-add, then the
 // rounding).
 struct SgdTarget {
@@ -153,21 +154,28 @@ struct SgdTarget {
   uint64_t seed;
 };
 
-// Four bf16 table values (columns c..c+3 of row key) after W - lr * g.
+// The 16-bit element type and rounding of a table MODE (2..5).
 template <int MODE>
-__device__ __forceinline__ uint2 bf16_updated(const SgdTarget& sgd, int64_t key, int c,
+constexpr int kModeElt = MODE >= 4 ? kEltF16 : kEltBF16;
+template <int MODE>
+constexpr bool kModeSR = MODE == 3 || MODE == 5;
+
+// Four 16-bit table values (columns c..c+3 of row key) after W - lr * g.
+template <int MODE>
+__device__ __forceinline__ uint2 half_updated(const SgdTarget& sgd, int64_t key, int c,
                                               float g0, float g1, float g2, float g3,
                                               uint2 w) {
-  const float n[4] = {__builtin_fmaf(-sgd.lr, g0, bf16_lo(w.x)),
-                      __builtin_fmaf(-sgd.lr, g1, bf16_hi(w.x)),
-                      __builtin_fmaf(-sgd.lr, g2, bf16_lo(w.y)),
-                      __builtin_fmaf(-sgd.lr, g3, bf16_hi(w.y))};
+  constexpr int TY = kModeElt<MODE>;
+  constexpr bool SR = kModeSR<MODE>;
+  const float n[4] = {__builtin_fmaf(-sgd.lr, g0, half_lo<TY>(w.x)),
+                      __builtin_fmaf(-sgd.lr, g1, half_hi<TY>(w.x)),
+                      __builtin_fmaf(-sgd.lr, g2, half_lo<TY>(w.y)),
+                      __builtin_fmaf(-sgd.lr, g3, half_hi<TY>(w.y))};
   uint32_t h[4];
   uint64_t bits = 0;
-  if constexpr (MODE == 3) bits = sr_bits4(sgd.seed, key, c, (int)(sgd.row_bytes >> 1));
+  if constexpr (SR) bits = sr_bits4(sgd.seed, key, c, (int)(sgd.row_bytes >> 1));
 #pragma unroll
-  for (int e = 0; e < 4; ++e)
-    h[e] = MODE == 3 ? f32_to_bf16_sr(n[e], sr_take(bits, e)) : f32_to_bf16_bits(n[e]);
+  for (int e = 0; e < 4; ++e) h[e] = to_half<TY, SR>(n[e], sr_take(bits, e));
   return make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
 }
 
@@ -183,7 +191,7 @@ struct SegSmem {
 };
 
 // Table-row part of one lane (4 columns) and its update W <- W - lr * g: one fused
-// multiply-add in fp32, then a plain store (fp32) or nearest-even to bf16.
+// multiply-add in fp32, then a plain store (fp32) or the 16-bit rounding of the MODE.
 template <int MODE>
 using WVec = typename std::conditional<(MODE >= 2), uint2, float4>::type;
 
@@ -208,7 +216,7 @@ __device__ __forceinline__ void store_updated(const SgdTarget& sgd, int64_t key,
                     __builtin_fmaf(-sgd.lr, g.z, x.z), __builtin_fmaf(-sgd.lr, g.w, x.w));
   } else if constexpr (MODE >= 2) {
     *reinterpret_cast<uint2*>(wrow + (int64_t)c * 2) =
-        bf16_updated<MODE>(sgd, key, c, g.x, g.y, g.z, g.w, x);
+        half_updated<MODE>(sgd, key, c, g.x, g.y, g.z, g.w, x);
   }
 }
 
@@ -390,7 +398,7 @@ __device__ __forceinline__ void reduce_chunk(
                             __builtin_fmaf(-sgd.lr, r.v[a][3], w.w));
         } else {
           uint2* wp = reinterpret_cast<uint2*>(wrow + (int64_t)c * 2);
-          *wp = bf16_updated<MODE>(sgd, key, c, r.v[a][0], r.v[a][1], r.v[a][2], r.v[a][3],
+          *wp = half_updated<MODE>(sgd, key, c, r.v[a][0], r.v[a][1], r.v[a][2], r.v[a][3],
                                    *wp);
         }
       }
@@ -811,6 +819,10 @@ hipError_t embbag_bwd_levels(const BwdWs& w, const void* grad, bool grad_bf16, i
       return segreduce_levels<2, S0>(s0, nnz, dim, row_grads, sgd, wm, s, l0_begin, l0_end);
     if (sgd_mode == 3)
       return segreduce_levels<3, S0>(s0, nnz, dim, row_grads, sgd, wm, s, l0_begin, l0_end);
+    if (sgd_mode == 4)
+      return segreduce_levels<4, S0>(s0, nnz, dim, row_grads, sgd, wm, s, l0_begin, l0_end);
+    if (sgd_mode == 5)
+      return segreduce_levels<5, S0>(s0, nnz, dim, row_grads, sgd, wm, s, l0_begin, l0_end);
     return segreduce_levels<0, S0>(s0, nnz, dim, row_grads, sgd, wm, s, l0_begin, l0_end);
   };
   const hipError_t e = grad_bf16 ? levels(L0SourceB{src, grad, sb, st, batch, num_bags})

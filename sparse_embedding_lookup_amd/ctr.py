@@ -18,7 +18,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.environ.get("CTR_LIB") or os.path.join(_HERE, "libctr.so")
 
 CTR_OK, CTR_ERR_INVALID_ARGUMENT, CTR_ERR_UNSUPPORTED, CTR_ERR_WORKSPACE_TOO_SMALL, CTR_ERR_HIP = range(5)
-CTR_F32, CTR_BF16 = 0, 1
+CTR_F32, CTR_BF16, CTR_F16 = 0, 1, 2
 CTR_I32, CTR_I64 = 0, 1
 
 EXPORTED = [
@@ -175,7 +175,9 @@ def _dtype_code(t: torch.Tensor) -> int:
         return CTR_F32
     if t.dtype == torch.bfloat16:
         return CTR_BF16
-    raise TypeError("table dtype must be float32 or bfloat16")
+    if t.dtype == torch.float16:
+        return CTR_F16
+    raise TypeError("dtype must be float32, bfloat16 or float16")
 
 
 def _index_code(t: torch.Tensor) -> int:

@@ -43,9 +43,9 @@ class FrontEnd:
         keep the per-row gradients in self.row_grads (always kept when not fused).
         pipelined: the unique outputs are double-buffered so that step_pipelined() can
         deduplicate the next batch's IDs while the current batch trains.
-        rounding: "nearest", or "stochastic" (bf16 tables): the k-th update of the run (the
-        native step k, or the k-th SGD stage run from Python) draws its rounding bits with
-        seed ctr_sr_step_seed(sr_seed, k).
+        rounding: "nearest", or "stochastic" (bf16 or fp16 tables): the k-th update of the
+        run (the native step k, or the k-th SGD stage run from Python) draws its rounding bits
+        with seed ctr_sr_step_seed(sr_seed, k).
         pad_r: R's rows start on 16-byte boundaries (stride rounded up to 4 floats), so that a
         layer reading R loads it with vector loads; R is then a strided view (the native step
         runner, which assumes contiguous R, refuses it).
@@ -53,7 +53,8 @@ class FrontEnd:
         interaction from an on-chip copy of the pooled vectors), instead of ctr_embbag_fwd
         then ctr_dot_interaction_fwd (pooled-interaction workloads only)."""
         assert rounding in ("nearest", "stochastic")
-        assert rounding == "nearest" or w.dtype == "bf16", "stochastic rounding: bf16 tables"
+        assert rounding == "nearest" or w.dtype in ("bf16", "f16"), \
+            "stochastic rounding: bf16 or fp16 tables"
         self.rounding = rounding
         self.sr_seed = sr_seed
         self._sr_k = 0
@@ -63,9 +64,8 @@ class FrontEnd:
         self.fused_fwd = bool(fused_fwd and w.interaction)
         self.keep_grads = keep_grads or not fused
         self.device = torch.device(device)
-        self.bf16 = w.dtype == "bf16"
         self.compute = ctr.CTR_BF16 if w.compute == "bf16" else ctr.CTR_F32
-        tdt = torch.bfloat16 if self.bf16 else torch.float32
+        tdt = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}[w.dtype]
         if table is None:
             table = torch.empty((w.total_rows, w.dim), dtype=tdt, device=self.device)
             ctr.ctr_init_tables_hash(table, w.rows, w.table_seed)

@@ -48,7 +48,7 @@ class Workload:
     num_tables: int
     rows: List[int]
     dim: int
-    dtype: str                # "f32" or "bf16" table storage
+    dtype: str                # table storage: "f32", "bf16" or "f16"
     batch: int
     indices: np.ndarray
     offsets: np.ndarray

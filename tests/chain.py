@@ -11,7 +11,7 @@ from tests.parity import (assert_close, assert_within, pool_eps, sgd_store_bound
 
 def host(t):
     torch.cuda.synchronize()
-    if t.dtype == torch.bfloat16:               # numpy has no bfloat16: widen (exact)
+    if t.dtype in (torch.bfloat16, torch.float16):   # widen (exact); numpy has no bfloat16
         t = t.float()
     return t.detach().cpu().numpy()
 
@@ -59,7 +59,6 @@ def check_chain(w, fe, o, table_rows=True):
     if table_rows:
         rows = torch.from_numpy(np.ascontiguousarray(o["uniq"])).to(fe.table.device)
         tbl = host(fe.table[rows].float())
-        assert_within(tbl, o["new"], sgd_store_bound(o["new"], o["gm"], w.lr, eb["g"],
-                                                     w.dtype == "bf16"),
+        assert_within(tbl, o["new"], sgd_store_bound(o["new"], o["gm"], w.lr, eb["g"], w.dtype),
                       "updated rows", mag=o["nm"])
     return eb

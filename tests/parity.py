@@ -6,7 +6,8 @@ derived below from how many roundings the kernel's arithmetic can put on a path.
 
 Notation (Higham, "Accuracy and Stability of Numerical Algorithms", 2nd ed., section 3.1 and
 chapter 4):
-  u    unit roundoff: U32 = 2^-24 for binary32, U16 = 2^-8 for bfloat16 (8 significand bits)
+  u    unit roundoff: U32 = 2^-24 for binary32, U16 = 2^-8 for bfloat16 (8 significand bits),
+       U16H = 2^-11 for binary16 (11 bits; below 2^-14 its spacing is 2^-24, an absolute error)
   g_k  gamma_k = k u / (1 - k u): k successive roundings give a relative error of at most g_k.
        A sum of n terms evaluated in ANY order (any binary tree of n leaves, depth <= n - 1)
        errs by at most g_{n-1} * sum |x_i|; a dot product of n terms, each product exact
@@ -22,8 +23,8 @@ Per-call bounds (both sides see the same inputs):
   segment reduce     g_D, D the depth of the reduce-by-key tree (segreduce_depth), which
                      does not grow with a segment's length
   SGD store          sgd_store_bound: fl32(w - lr g) once (fp32 tables), then nearest-even
-                     to bf16 (bf16 tables: a double rounding), against the oracle's single
-                     rounding of the exact value
+                     to bf16 or fp16 (16-bit tables: a double rounding), against the oracle's
+                     single rounding of the exact value
 
 Chained bounds (one step end to end against the oracle's own chain): each stage's input
 error enters its output through the stage's arithmetic (linear stages pass it through, the
@@ -36,6 +37,7 @@ RTOL_F32 = 1e-5          # the per-call figure for fp32 arithmetic
 RTOL_BF16 = 1e-2         # the per-call figure for bf16 storage / bf16 operands
 U32 = 2.0 ** -24
 U16 = 2.0 ** -8
+U16H = 2.0 ** -11        # binary16 (11 significant bits)
 
 
 def gamma(k, u=U32):
@@ -91,15 +93,27 @@ def store_bound(want, mag, eps, store_bf16):
     return eps * mag * (1.0 + U16) + U16 * want
 
 
-def sgd_store_bound(new, gmag, lr, eps_g, table_bf16):
+# Unit roundoff and half the subnormal spacing (the absolute error of a nearest rounding in
+# the subnormal range) of the table storage types.
+STORE_U = {"f32": U32, "bf16": U16, "f16": U16H}
+STORE_ETA = {"f32": 0.0, "bf16": 0.0, "f16": 2.0 ** -25}
+
+
+def sgd_store_bound(new, gmag, lr, eps_g, table):
     """Bound of |W'_gpu - W'_oracle| per element.  The oracle stores s1(x) with x = w - lr g
     exact and s1 one rounding to the table type; the kernel stores s2(fl32(w - lr g~)) with
-    |g~ - g| <= eps_g * gmag (one fused multiply-add, then nearest-even for bf16)."""
-    s1 = U16 if table_bf16 else U32
-    s2 = (U16 + U32 + U16 * U32) if table_bf16 else U32
-    x = np.abs(np.asarray(new, np.float64)) / (1.0 - s1)
+    |g~ - g| <= eps_g * gmag (one fused multiply-add, then nearest-even for a 16-bit table).
+    A rounding s to the table type errs by at most u|z| + eta (eta: binary16's subnormal
+    range, where the spacing is 2^-24 whatever |z|).  table: "f32", "bf16", "f16" (or a bool,
+    True for bf16)."""
+    if isinstance(table, (bool, np.bool_)):
+        table = "bf16" if table else "f32"
+    u, eta = STORE_U[table], STORE_ETA[table]
+    s1 = u
+    s2 = U32 if table == "f32" else (u + U32 + u * U32)
+    x = (np.abs(np.asarray(new, np.float64)) + eta) / (1.0 - s1)
     dg = float(lr) * eps_g * np.asarray(gmag, np.float64)
-    return dg + s2 * (x + dg) + s1 * x
+    return dg + s2 * (x + dg) + s1 * x + 2.0 * eta
 
 
 def step_bounds(max_bag, dim, F, n, compute_bf16, grad_bf16):

@@ -101,6 +101,8 @@ def test_embbag_fwd_bad_args():
     assert call(dtype=5) == ctr.CTR_ERR_INVALID_ARGUMENT
     assert call(dim=6) == ctr.CTR_ERR_UNSUPPORTED              # not a 16-byte multiple (fp32)
     assert call(dtype=1, dim=12) == ctr.CTR_ERR_UNSUPPORTED    # bf16 needs multiples of 8
+    assert call(dtype=ctr.CTR_F16, dim=12) == ctr.CTR_ERR_UNSUPPORTED   # so does fp16
+    assert call(dtype=3) == ctr.CTR_ERR_INVALID_ARGUMENT
     assert call(table=MISALIGNED) == ctr.CTR_ERR_UNSUPPORTED
     assert call(out=MISALIGNED) == ctr.CTR_ERR_UNSUPPORTED
     assert call(sb=18) == ctr.CTR_ERR_UNSUPPORTED
@@ -127,6 +129,8 @@ def test_embbag_interaction_fwd_bad_args():
     assert call(table=None) == ctr.CTR_ERR_INVALID_ARGUMENT
     assert call(dtype=5) == ctr.CTR_ERR_INVALID_ARGUMENT
     assert call(dim=6) == ctr.CTR_ERR_UNSUPPORTED              # not a 16-byte multiple
+    assert call(dtype=ctr.CTR_F16) == ctr.CTR_ERR_UNSUPPORTED  # fp16 tables: separate calls
+    assert b"CTR_F16" in lib.ctr_last_error_message()
     assert call(it=3) == ctr.CTR_ERR_INVALID_ARGUMENT
     assert call(T=0) == ctr.CTR_ERR_INVALID_ARGUMENT
     assert call(nnz=-1) == ctr.CTR_ERR_INVALID_ARGUMENT
@@ -217,6 +221,12 @@ def test_rounding_argument_bad_args():
     assert lib.ctr_sparse_sgd(FAKE, ctr.CTR_BF16, 100, 16, FAKE, FAKE, 10, FAKE,
                               ctypes.c_float(0.01), 5, s0, None) == ctr.CTR_ERR_INVALID_ARGUMENT
     assert b"rounding" in lib.ctr_last_error_message()
+    # fp16 tables take both roundings (the query of the fused backward answers)
+    wsb = ctypes.c_size_t(0)
+    assert lib.ctr_embbag_bwd_sgd(None, ctr.CTR_F32, 64, 0, None, 10, 1, 100, None, None, FAKE,
+                                  ctr.CTR_F16, 1000, 16, None, ctypes.c_float(0.01), SR, s0,
+                                  None, None, ctypes.byref(wsb), None) == ctr.CTR_OK
+    assert wsb.value > 0
     wsb = ctypes.c_size_t(0)
     bwd = lib.ctr_embbag_bwd_sgd
     st = bwd(FAKE, ctr.CTR_F32, 64, 0, FAKE, 10, 1, 100, FAKE, FAKE, FAKE, ctr.CTR_F32, 1000, 16,

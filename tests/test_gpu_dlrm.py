@@ -106,7 +106,7 @@ def test_dlrm_step_stage_by_stage(name):
     new, nm = orc.sparse_sgd(tab, uniq, g, gm, w.lr)
     rows = _f32(s.fe.table)[uniq]
     eg = gamma(segreduce_depth(w.nnz, w.dim, s.fe.dZ.dtype == torch.bfloat16))
-    assert_within(rows, new, sgd_store_bound(new, gm, w.lr, eg, w.dtype == "bf16"), "table rows",
+    assert_within(rows, new, sgd_store_bound(new, gm, w.lr, eg, w.dtype), "table rows",
                   mag=nm)
 
     # backward through the bottom MLP, starting from dZ[:, 0, :]

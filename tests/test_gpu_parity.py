@@ -35,7 +35,7 @@ def dev(a):
 
 def host(t):
     torch.cuda.synchronize()
-    if t.dtype == torch.bfloat16:               # numpy has no bfloat16: widen (exact)
+    if t.dtype in (torch.bfloat16, torch.float16):   # widen (exact); numpy has no bfloat16
         t = t.float()
     return t.detach().cpu().numpy()
 
@@ -50,15 +50,18 @@ def rand_csr(rng, T, B, rows, max_len, empty_frac=0.0):
     return ids.astype(np.int64), off
 
 
+TORCH_DTYPE = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}
+
+
 def gpu_table(rows, dim, dtype, seed):
-    t = torch.empty((int(sum(rows)), dim),
-                    dtype=torch.bfloat16 if dtype == "bf16" else torch.float32, device=DEV)
+    t = torch.empty((int(sum(rows)), dim), dtype=TORCH_DTYPE[dtype], device=DEV)
     ctr.ctr_init_tables_hash(t, rows, seed)
     return t
 
 
 # ----------------------------------------------------------------------------- table fill
-@pytest.mark.parametrize("dtype,dim", [("f32", 16), ("bf16", 128), ("f32", 4)])
+@pytest.mark.parametrize("dtype,dim", [("f32", 16), ("bf16", 128), ("f32", 4), ("f16", 64),
+                                       ("f16", 8)])
 def test_table_fill_matches_oracle_definition(dtype, dim):
     say("table fill", dtype, dim)
     rows = [1000, 37, 5000]
@@ -186,7 +189,7 @@ def test_unique_empty():
 
 
 # ----------------------------------------------------------------------------- gather rows
-@pytest.mark.parametrize("dtype,dim", [("f32", 32), ("bf16", 128), ("f32", 4)])
+@pytest.mark.parametrize("dtype,dim", [("f32", 32), ("bf16", 128), ("f32", 4), ("f16", 16)])
 def test_gather_rows_bit_exact(dtype, dim):
     say("gather", dtype, dim)
     rows = [20_000]
@@ -233,6 +236,16 @@ def _fwd_case(name):
         rows = [7, 50_000, 300]
         ids, off = rand_csr(rng, 3, 1001, rows, 64, empty_frac=0.1)
         return rows, 64, "f32", ids, off, 1001, 3
+    if name == "f16_d32_tables":
+        # binary16 storage: rows of small tables, so the fill's values (|x| <= rows^-1/2)
+        # reach binary16's subnormal range
+        rows = [60_000, 900, 40_000]
+        ids, off = rand_csr(rng, 3, 257, rows, 40, empty_frac=0.05)
+        return rows, 32, "f16", ids, off, 257, 3
+    if name == "f16_d256":
+        rows = [3000]
+        ids, off = rand_csr(rng, 1, 300, rows, 9)
+        return rows, 256, "f16", ids, off, 300, 1
     if name == "one_bag_200k":
         rows = [100_000]
         off = np.array([0, 200_000], dtype=np.int64)
@@ -249,7 +262,7 @@ def _fwd_case(name):
 
 
 FWD_CASES = ["tiny", "small_b512", "criteo_b512", "empty_bags_d4", "bf16_d8_long", "f32_d512",
-             "mixed_tables_d64", "one_bag_200k", "one_bag_1m_d4"]
+             "mixed_tables_d64", "one_bag_200k", "one_bag_1m_d4", "f16_d32_tables", "f16_d256"]
 
 
 @pytest.mark.parametrize("name", FWD_CASES)
@@ -399,7 +412,8 @@ def test_embbag_bwd_matches_oracle(name):
 
 
 # ----------------------------------------------------------------------------- SGD
-@pytest.mark.parametrize("dtype,dim", [("f32", 64), ("bf16", 128), ("f32", 4)])
+@pytest.mark.parametrize("dtype,dim", [("f32", 64), ("bf16", 128), ("f32", 4), ("f16", 64),
+                                       ("f16", 8)])
 def test_sparse_sgd_matches_oracle(dtype, dim):
     say("sgd", dtype, dim)
     rows = [4000, 3000]
@@ -418,7 +432,7 @@ def test_sparse_sgd_matches_oracle(dtype, dim):
     ctr.ctr_sparse_sgd(t, dev(uq), dev(np.array([U], np.int32)), cap, dev(gg), 0.01)
     after = host(t.float())
     want, mag = orc.sparse_sgd(tab, uniq, g.astype(np.float64), np.abs(g).astype(np.float64), 0.01)
-    assert_within(after[uniq], want, sgd_store_bound(want, np.abs(g), 0.01, 0.0, dtype == "bf16"),
+    assert_within(after[uniq], want, sgd_store_bound(want, np.abs(g), 0.01, 0.0, dtype),
                   "sgd rows", mag=mag)
     untouched = np.ones(7000, bool)
     untouched[uniq] = False
