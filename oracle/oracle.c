@@ -446,6 +446,81 @@ void orc_interaction_self_bwd(const double* Z, const double* zmag, const double*
   }
 }
 
+/* [DHEN] 3.3, eq. (7): a DCN-style layer takes the whole Gram matrix X X^T of a sample's
+ * vectors.  R[b][dim + i F + j] = <z_i, z_j> for all i, j < F (row-major, both triangles and
+ * the diagonal), after the dense slot R[b][0 .. dim) = z_0.  Magnitudes and the bf16 factors
+ * as in orc_interaction_fwd.  R, rmag: [batch][dim + F F]. */
+void orc_interaction_gram_fwd(const double* Z, const double* zmag, int64_t batch, int32_t F,
+                              int32_t dim, int32_t bf16, double* R, double* rmag) {
+  int64_t P = (int64_t)F * F, W = dim + P;
+#pragma omp parallel for schedule(static)
+  for (int64_t b = 0; b < batch; ++b) {
+    const double* z = Z + b * F * dim;
+    const double* zm = zmag ? zmag + b * F * dim : NULL;
+    for (int64_t c = 0; c < dim; ++c) {
+      R[b * W + c] = z[c];
+      rmag[b * W + c] = zm ? zm[c] : fabs(z[c]);
+    }
+    for (int64_t i = 0; i < F; ++i)
+      for (int64_t j = 0; j < F; ++j) {
+        double s = 0.0, a = 0.0;
+        for (int64_t c = 0; c < dim; ++c) {
+          double xi = operand(z[i * dim + c], bf16), xj = operand(z[j * dim + c], bf16);
+          s += xi * xj;
+          double mi = zm ? zm[i * dim + c] : fabs(xi);
+          double mj = zm ? zm[j * dim + c] : fabs(xj);
+          a += mi * mj;
+        }
+        R[b * W + dim + i * F + j] = s;
+        rmag[b * W + dim + i * F + j] = a;
+      }
+  }
+}
+
+/* Chain rule of the Gram matrix: <z_i, z_j> sits at (i, j) and (j, i), so
+ * dZ_i = sum over j of (dG_ij + dG_ji) z_j (on the diagonal 2 dG_ii z_i), plus the dense
+ * passthrough's gradient on dZ_0.  Without bf16 the factor S_ij = dG_ij + dG_ji is exact here;
+ * with bf16 != 0 it is formed as a matrix-core kernel takes it, the binary32 sum of the two
+ * binary32 gradients rounded to bf16 (the reading for bf16 workloads, orc_interaction_bwd), and
+ * z_j is rounded to bf16; products and sums stay exact.  Magnitude per term:
+ * (|dG_ij| + |dG_ji|) |z_j| (|S_ij| |z_j| with bf16).  dR: [batch][dim + F F]. */
+void orc_interaction_gram_bwd(const double* Z, const double* zmag, const double* dR,
+                              int64_t batch, int32_t F, int32_t dim, int32_t bf16, double* dZ,
+                              double* dmag) {
+  int64_t P = (int64_t)F * F, W = dim + P;
+#pragma omp parallel for schedule(static)
+  for (int64_t b = 0; b < batch; ++b) {
+    const double* z = Z + b * F * dim;
+    const double* zm = zmag ? zmag + b * F * dim : NULL;
+    const double* g = dR + b * W + dim;
+    for (int64_t i = 0; i < F; ++i)
+      for (int64_t c = 0; c < dim; ++c) {
+        double s = 0.0, a = 0.0;
+        for (int64_t j = 0; j < F; ++j) {
+          double gij = g[i * F + j], gji = g[j * F + i];
+          double sij, mij;
+          if (bf16) {
+            float s32 = (float)gij + (float)gji;          /* binary32 sum, one rounding */
+            sij = orc_round_bf16((double)s32);
+            mij = fabs(sij);
+          } else {
+            sij = gij + gji;
+            mij = fabs(gij) + fabs(gji);
+          }
+          double zj = operand(z[j * dim + c], bf16);
+          s += sij * zj;
+          a += mij * (zm ? zm[j * dim + c] : fabs(zj));
+        }
+        if (i == 0) {
+          s += dR[b * W + c];
+          a += fabs(dR[b * W + c]);
+        }
+        dZ[(b * F + i) * dim + c] = s;
+        dmag[(b * F + i) * dim + c] = a;
+      }
+  }
+}
+
 /* [DHEN] Solution 2, the FM sum: out[b] = sum over F > i > j >= 0 of <z_i, z_j>, written as
  * that definition (O(F^2 d)).  The magnitude also counts 1/2 sum_i ||z_i||^2: the O(F d)
  * squared-norm form 1/2 (||sum z_i||^2 - sum ||z_i||^2) cancels those self terms, and a

@@ -65,6 +65,8 @@ def _load():
         "orc_sparse_sgd": (None, [P, u64, P, i32, i32, i32, P, i64, P, P, f32, P, P]),
         "orc_interaction_self_fwd": (None, [P, P, i64, i32, i32, i32, P, P]),
         "orc_interaction_self_bwd": (None, [P, P, P, i64, i32, i32, i32, P, P]),
+        "orc_interaction_gram_fwd": (None, [P, P, i64, i32, i32, i32, P, P]),
+        "orc_interaction_gram_bwd": (None, [P, P, P, i64, i32, i32, i32, P, P]),
         "orc_fm_fwd": (None, [P, P, i64, i32, i32, P, P]),
         "orc_fm_bwd": (None, [P, P, P, i64, i32, i32, P, P]),
         "orc_dense_fwd": (None, [P, P, i64, i32, P, P, i32, i32, i32, P, P]),
@@ -258,6 +260,30 @@ def interaction_self_bwd(Z, dR, zmag=None, bf16: bool = False):
     dZ = np.empty((B, F, d), dtype=np.float64)
     dm = np.empty_like(dZ)
     _load().orc_interaction_self_bwd(_p(Z), _p(zm), _p(dR), B, F, d, int(bool(bf16)), _p(dZ),
+                                     _p(dm))
+    return dZ, dm
+
+
+def interaction_gram_fwd(Z, zmag=None, bf16: bool = False):
+    """The whole Gram matrix, P = F^2 row-major: R = [dense | G], with magnitudes."""
+    Z = _c(Z, np.float64)
+    B, F, d = Z.shape
+    zm = None if zmag is None else _c(zmag, np.float64)
+    R = np.empty((B, d + F * F), dtype=np.float64)
+    Rm = np.empty_like(R)
+    _load().orc_interaction_gram_fwd(_p(Z), _p(zm), B, F, d, int(bool(bf16)), _p(R), _p(Rm))
+    return R, Rm
+
+
+def interaction_gram_bwd(Z, dR, zmag=None, bf16: bool = False):
+    """dZ of the Gram matrix: dZ_i = sum_j (dG_ij + dG_ji) z_j (+ dense on dZ_0)."""
+    Z = _c(Z, np.float64)
+    B, F, d = Z.shape
+    dR = _c(dR, np.float64)
+    zm = None if zmag is None else _c(zmag, np.float64)
+    dZ = np.empty((B, F, d), dtype=np.float64)
+    dm = np.empty_like(dZ)
+    _load().orc_interaction_gram_bwd(_p(Z), _p(zm), _p(dR), B, F, d, int(bool(bf16)), _p(dZ),
                                      _p(dm))
     return dZ, dm
 

@@ -1,6 +1,6 @@
 """Pins of the oracle's interaction variants ("DHEN" notes, 3.1: inner products for i <= j;
-Solution 2: the FM sum by the squared-norm identity) against facts that do not come from
-the oracle's own loops.
+Solution 2: the FM sum by the squared-norm identity; 3.3, eq. (7): the whole Gram matrix)
+against facts that do not come from the oracle's own loops.
 
 * The forward values are checked against a library routine (numpy matmul of Z with its
   transpose, the Gram matrix), read at the documented pair positions.
@@ -106,3 +106,79 @@ def test_fm_bwd_is_the_derivative(F, d):
     want = _fd_grad(lambda z: float((orc.fm_fwd(z)[0] * dout).sum()), Z)
     np.testing.assert_allclose(dZ, want, rtol=1e-10, atol=1e-10)
     assert np.all(dm >= np.abs(dZ) - 1e-12)
+
+
+# ----------------------------------------------------------------------------- Gram matrix
+# "DHEN" notes, 3.3, eq. (7): a DCN-style layer takes the whole Gram matrix X X^T.
+
+@pytest.mark.parametrize("B,F,d", [(3, 1, 4), (4, 5, 8), (2, 17, 3), (1, 33, 2)])
+def test_gram_fwd_is_the_gram_matrix(B, F, d):
+    rng = np.random.default_rng(F * 7 + d)
+    Z = rng.standard_normal((B, F, d))
+    R, Rm = orc.interaction_gram_fwd(Z)
+    assert R.shape == (B, d + F * F)
+    np.testing.assert_array_equal(R[:, :d], Z[:, 0])
+    G = R[:, d:].reshape(B, F, F)
+    np.testing.assert_allclose(G, _gram(Z), rtol=1e-13, atol=1e-13)
+    np.testing.assert_array_equal(G, np.transpose(G, (0, 2, 1)))          # symmetric exactly
+    np.testing.assert_allclose(np.diagonal(G, axis1=1, axis2=2), (Z ** 2).sum(-1), rtol=1e-13)
+    np.testing.assert_allclose(Rm[:, d:].reshape(B, F, F), _gram(np.abs(Z)), rtol=1e-13)
+    # its lower triangle with the diagonal is the self-dot pair set, value for value
+    Rs, _ = orc.interaction_self_fwd(Z)
+    si, sj = np.tril_indices(F, 0)
+    np.testing.assert_array_equal(G[:, si, sj], Rs[:, d:])
+
+
+@pytest.mark.parametrize("F,d", [(1, 3), (4, 2), (6, 3)])
+def test_gram_bwd_is_the_derivative(F, d):
+    rng = np.random.default_rng(F + 100 * d)
+    B = 2
+    Z = rng.standard_normal((B, F, d))
+    dR = rng.standard_normal((B, d + F * F))
+    dZ, dm = orc.interaction_gram_bwd(Z, dR)
+    want = _fd_grad(lambda z: float((orc.interaction_gram_fwd(z)[0] * dR).sum()), Z)
+    np.testing.assert_allclose(dZ, want, rtol=1e-10, atol=1e-10)
+    assert np.all(dm >= np.abs(dZ) - 1e-12)
+
+
+def test_gram_bwd_of_a_lower_triangle_is_the_self_bwd():
+    """dG zero above the diagonal: S_ij = dG_(max,min), S_ii = 2 dG_ii, the self-dot set's
+    chain rule exactly."""
+    rng = np.random.default_rng(8)
+    B, F, d = 3, 7, 5
+    Z = rng.standard_normal((B, F, d))
+    dRs = rng.standard_normal((B, d + F * (F + 1) // 2))
+    dG = np.zeros((B, F, F))
+    si, sj = np.tril_indices(F, 0)
+    dG[:, si, sj] = dRs[:, d:]
+    dR = np.concatenate([dRs[:, :d], dG.reshape(B, F * F)], axis=1)
+    for bf16 in (False, True):
+        got, _ = orc.interaction_gram_bwd(Z, dR, bf16=bf16)
+        want, _ = orc.interaction_self_bwd(Z, dRs, bf16=bf16)
+        np.testing.assert_array_equal(got, want)
+
+
+def test_gram_bf16_operands_against_torch_cast():
+    """bf16 mode: factors rounded with torch's own cast; the backward's S_ij is the binary32
+    sum of the two mirrored gradients (numpy float32 addition), then rounded."""
+    import torch
+
+    def bf(x):
+        return torch.from_numpy(np.asarray(x, np.float64)).to(torch.bfloat16).double().numpy()
+
+    rng = np.random.default_rng(31)
+    B, F, d = 3, 9, 16
+    Z = rng.standard_normal((B, F, d))
+    dR = rng.standard_normal((B, d + F * F)).astype(np.float32).astype(np.float64)
+    Zb = bf(Z)
+    R, _ = orc.interaction_gram_fwd(Z, bf16=True)
+    np.testing.assert_allclose(R[:, d:].reshape(B, F, F), _gram(Zb), rtol=1e-13, atol=1e-13)
+    g = dR[:, d:].reshape(B, F, F).astype(np.float32)
+    S = bf((g + np.transpose(g, (0, 2, 1))).astype(np.float64))      # float32 sums
+    want = np.matmul(S, Zb)
+    want[:, 0, :] += dR[:, :d]
+    dZ, dm = orc.interaction_gram_bwd(Z, dR, bf16=True)
+    np.testing.assert_allclose(dZ, want, rtol=1e-12, atol=1e-12)
+    wm = np.matmul(np.abs(S), np.abs(Zb))
+    wm[:, 0, :] += np.abs(dR[:, :d])
+    np.testing.assert_allclose(dm, wm, rtol=1e-12)
