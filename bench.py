@@ -173,9 +173,9 @@ class TimingEvent:
 
 
 def cpu_baseline_variants(fe, w, seconds: float):
-    """The oracle's interaction variants (self-dot pairs and the FM sum, forward and
-    backward) on the first samples of the workload's Z, repeated until `seconds` in total;
-    samples per second for each call."""
+    """The oracle's interaction variants (self-dot pairs, the Gram matrix and the FM sum,
+    forward and backward) on the first samples of the workload's Z, repeated until `seconds`
+    in total; samples per second for each call."""
     import numpy as np
     from oracle import oracle as orc
 
@@ -184,9 +184,13 @@ def cpu_baseline_variants(fe, w, seconds: float):
     rng = np.random.default_rng(9)
     Zs = fe.Z[:min(B, 4096)].double().cpu().numpy()
     dR = rng.standard_normal((Zs.shape[0], d + P))
+    dRg = rng.standard_normal((Zs.shape[0], d + F * F))
     dout = rng.standard_normal(Zs.shape[0])
     calls = {"interaction_self_fwd": lambda z, r, o: orc.interaction_self_fwd(z),
              "interaction_self_bwd": lambda z, r, o: orc.interaction_self_bwd(z, r),
+             "interaction_gram_fwd": lambda z, r, o: orc.interaction_gram_fwd(z),
+             "interaction_gram_bwd": lambda z, r, o: orc.interaction_gram_bwd(
+                 z, dRg[:z.shape[0]]),
              "fm_fwd": lambda z, r, o: orc.fm_fwd(z),
              "fm_bwd": lambda z, r, o: orc.fm_bwd(z, o)}
     res = {}
@@ -211,11 +215,12 @@ def cpu_baseline_variants(fe, w, seconds: float):
 def time_variants(fe, w, K: int):
     """The interaction variants on the workload's Z (after the timed steps), each call alone
     bracketed by HIP events: the pair set with self-dots, forward and backward (P = F(F+1)/2),
-    and the FM sum by the squared-norm identity; and the fused forward (pooling and the
-    interaction in one call) beside the two calls it replaces, timed the same way.
-    Algorithmic bytes: self forward 4BFd + 4B(d+P), backward 4B(d+P) + 8BFd; FM forward
-    4BFd + 4B, backward 8BFd + 4B; fused forward the pooling's bytes plus the dense rows read
-    (4Bd) and R written (4B(d+P)), the separate pair that plus Z's re-read (4BFd)."""
+    the whole Gram matrix (P = F^2), and the FM sum by the squared-norm identity; and the fused
+    forward (pooling and the interaction in one call) beside the two calls it replaces, timed
+    the same way.  Algorithmic bytes: self and Gram forward 4BFd + 4B(d+P), backward
+    4B(d+P) + 8BFd; FM forward 4BFd + 4B, backward 8BFd + 4B; fused forward the pooling's
+    bytes plus the dense rows read (4Bd) and R written (4B(d+P)), the separate pair that plus
+    Z's re-read (4BFd)."""
     import torch
     from sparse_embedding_lookup_amd import ctr
 
@@ -225,6 +230,9 @@ def time_variants(fe, w, K: int):
     dR = torch.randn((B, d + P), generator=gen, device="cuda")
     dout = torch.randn((B,), generator=gen, device="cuda")
     R = torch.empty((B, d + P), device="cuda")
+    Pg = F * F
+    dRg = torch.randn((B, d + Pg), generator=gen, device="cuda")
+    Rg = torch.empty((B, d + Pg), device="cuda")
     dZ = torch.empty_like(fe.Z)
     out = torch.empty((B,), device="cuda")
     calls = {
@@ -233,6 +241,12 @@ def time_variants(fe, w, K: int):
         "interaction_self_bwd": (ctr.ctr_dot_interaction_self_bwd(fe.Z, dR, fe.compute, dZ,
                                                                   prepare=True),
                                  4 * B * (d + P) + 8 * B * F * d),
+        "interaction_gram_fwd": (ctr.ctr_dot_interaction_gram_fwd(fe.Z, fe.compute, Rg,
+                                                                  prepare=True),
+                                 4 * B * F * d + 4 * B * (d + Pg)),
+        "interaction_gram_bwd": (ctr.ctr_dot_interaction_gram_bwd(fe.Z, dRg, fe.compute, dZ,
+                                                                  prepare=True),
+                                 4 * B * (d + Pg) + 8 * B * F * d),
         "fm_fwd": (ctr.ctr_fm_interaction_fwd(fe.Z, out, prepare=True), 4 * B * F * d + 4 * B),
         "fm_bwd": (ctr.ctr_fm_interaction_bwd(fe.Z, dout, dZ, prepare=True),
                    8 * B * F * d + 4 * B),

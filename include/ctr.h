@@ -311,6 +311,26 @@ int32_t ctr_dot_interaction_self_bwd(const float* Z, const float* dR, int64_t dr
                                      int32_t compute, int32_t dz_dtype, void* dZ, void* stream);
 
 /*
+ * ctr_dot_interaction_gram_fwd / _gram_bwd -- the whole Gram matrix X X^T that a DCN-style
+ * layer takes ([DHEN] 3.3, eq. (7): all pairwise interactions as an F x F matrix), both
+ * triangles and the diagonal, row-major after the dense slot:
+ *   R[b*r_stride + c]                 = Z[b, 0, c]                        c < dim
+ *   R[b*r_stride + dim + i*F + j]     = <Z[b, i, :], Z[b, j, :]>          i, j < F
+ * The dot of i > j is computed once and stored at (i, j) and (j, i), so the matrix is exactly
+ * symmetric.  Backward, with dG_ij = dR[b*dr_stride + dim + i*F + j]:
+ *   dZ[b, i, :] = sum over j of S_ij * Z[b, j, :] + (i == 0 ? dR[b*dr_stride + 0 .. dim) : 0)
+ *   S_ij = dG_ij + dG_ji in binary32 (S_ii = 2 dG_ii); compute = CTR_BF16 rounds S and Z to
+ *   bf16 for the matrix cores.
+ * r_stride, dr_stride >= dim + F*F; F >= 1; otherwise as ctr_dot_interaction_fwd/bwd.
+ */
+int32_t ctr_dot_interaction_gram_fwd(const float* Z, int64_t batch, int32_t num_vectors,
+                                     int32_t dim, int32_t compute, float* R, int64_t r_stride,
+                                     void* stream);
+int32_t ctr_dot_interaction_gram_bwd(const float* Z, const float* dR, int64_t dr_stride,
+                                     int64_t batch, int32_t num_vectors, int32_t dim,
+                                     int32_t compute, int32_t dz_dtype, void* dZ, void* stream);
+
+/*
  * ctr_fm_interaction_fwd / _bwd -- the sum of all pair dots by the squared-norm identity,
  * [DHEN] Solution 2 (the FM trick), O(F * dim) per sample instead of O(F^2 * dim):
  *   out[b] = sum over F > i > j >= 0 of <Z[b,i,:], Z[b,j,:]>

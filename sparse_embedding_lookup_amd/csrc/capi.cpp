@@ -457,62 +457,67 @@ uint64_t ctr_sr_step_seed(uint64_t base, int64_t k) {
   return z ^ (z >> 31);
 }
 
+// pairs: ctr::kPairStrict, kPairSelf or kPairGram (the interaction's pair set).
 static int32_t check_interaction(const float* Z, int64_t batch, int32_t F, int32_t dim,
-                                 int32_t compute, bool self, const float* out, int64_t stride) {
+                                 int32_t compute, int pairs, const float* out, int64_t stride) {
   if (batch < 0 || batch > kMaxElems) return fail(CTR_ERR_INVALID_ARGUMENT, "bad batch");
-  if (F < (self ? 1 : 2))
-    return fail(CTR_ERR_INVALID_ARGUMENT, "num_vectors must be >= %d (got %d)", self ? 1 : 2, F);
+  const int fmin = pairs == ctr::kPairStrict ? 2 : 1;
+  if (F < fmin)
+    return fail(CTR_ERR_INVALID_ARGUMENT, "num_vectors must be >= %d (got %d)", fmin, F);
+  if (F > 4096) return fail(CTR_ERR_UNSUPPORTED, "num_vectors %d above 4096", F);
   if (dim <= 0) return fail(CTR_ERR_INVALID_ARGUMENT, "dim must be positive");
   if (compute != CTR_F32 && compute != CTR_BF16)
     return fail(CTR_ERR_INVALID_ARGUMENT, "compute %d is not CTR_F32 or CTR_BF16", compute);
   if (batch > 0 && (!Z || !out)) return fail(CTR_ERR_INVALID_ARGUMENT, "Z and output are required");
-  const int64_t P = self ? (int64_t)F * (F + 1) / 2 : (int64_t)F * (F - 1) / 2;
+  const int64_t P = pairs == ctr::kPairGram   ? (int64_t)F * F
+                    : pairs == ctr::kPairSelf ? (int64_t)F * (F + 1) / 2
+                                              : (int64_t)F * (F - 1) / 2;
   if (stride < dim + P) return fail(CTR_ERR_INVALID_ARGUMENT, "stride %lld < dim + P", (long long)stride);
   if (compute == CTR_BF16) {
-    if (!ctr::interaction_bf16_supported(F, dim, self))
+    if (!ctr::interaction_bf16_supported(F, dim, pairs))
       return fail(CTR_ERR_UNSUPPORTED, "bf16 path needs dim in {16,32,64,128}, F <= 128");
     if (Z && !aligned16(Z)) return fail(CTR_ERR_UNSUPPORTED, "Z is not 16-byte aligned");
-  } else if (!ctr::interaction_f32_supported(F, dim, self)) {
+  } else if (!ctr::interaction_f32_supported(F, dim, pairs)) {
     return fail(CTR_ERR_UNSUPPORTED, "fp32 path: one sample of F=%d, dim=%d exceeds 64 KiB of LDS", F, dim);
   }
   return CTR_OK;
 }
 
 static int32_t interaction_fwd_common(const float* Z, int64_t batch, int32_t F, int32_t dim,
-                                      int32_t compute, bool self, float* R, int64_t r_stride,
+                                      int32_t compute, int pairs, float* R, int64_t r_stride,
                                       void* stream, const char* name) {
   g_msg[0] = 0;
-  int32_t st = check_interaction(Z, batch, F, dim, compute, self, R, r_stride);
+  int32_t st = check_interaction(Z, batch, F, dim, compute, pairs, R, r_stride);
   if (st) return st;
-  return hip_status(ctr::launch_interaction_fwd(Z, batch, F, dim, compute == CTR_BF16, self, R,
+  return hip_status(ctr::launch_interaction_fwd(Z, batch, F, dim, compute == CTR_BF16, pairs, R,
                                                 r_stride, (hipStream_t)stream),
                     name);
 }
 
 static int32_t interaction_bwd_common(const float* Z, const float* dR, int64_t dr_stride,
                                       int64_t batch, int32_t F, int32_t dim, int32_t compute,
-                                      bool self, int32_t dz_dtype, void* dZ, void* stream,
+                                      int pairs, int32_t dz_dtype, void* dZ, void* stream,
                                       const char* name) {
   g_msg[0] = 0;
   if (dz_dtype != CTR_F32 && dz_dtype != CTR_BF16)
     return fail(CTR_ERR_INVALID_ARGUMENT, "dz_dtype %d is not CTR_F32 or CTR_BF16", dz_dtype);
   const bool dz_bf16 = dz_dtype == CTR_BF16;
-  int32_t st = check_interaction(Z, batch, F, dim, compute, self, static_cast<const float*>(dZ),
+  int32_t st = check_interaction(Z, batch, F, dim, compute, pairs, static_cast<const float*>(dZ),
                                  dr_stride);
   if (st) return st;
   if (batch > 0 && !dR) return fail(CTR_ERR_INVALID_ARGUMENT, "dR is NULL");
   if (dz_bf16 && compute != CTR_BF16)
     return fail(CTR_ERR_UNSUPPORTED, "a bf16 dZ needs compute = CTR_BF16");
   return hip_status(ctr::launch_interaction_bwd(Z, dR, dr_stride, batch, F, dim,
-                                                compute == CTR_BF16, self, dz_bf16, dZ,
+                                                compute == CTR_BF16, pairs, dz_bf16, dZ,
                                                 (hipStream_t)stream),
                     name);
 }
 
 int32_t ctr_dot_interaction_fwd(const float* Z, int64_t batch, int32_t num_vectors, int32_t dim,
                                 int32_t compute, float* R, int64_t r_stride, void* stream) {
-  return interaction_fwd_common(Z, batch, num_vectors, dim, compute, false, R, r_stride, stream,
-                                "ctr_dot_interaction_fwd");
+  return interaction_fwd_common(Z, batch, num_vectors, dim, compute, ctr::kPairStrict, R,
+                                r_stride, stream, "ctr_dot_interaction_fwd");
 }
 
 int32_t ctr_embbag_interaction_fwd(const void* table, int32_t dtype, int64_t total_rows,
@@ -557,22 +562,38 @@ int32_t ctr_embbag_interaction_fwd(const void* table, int32_t dtype, int64_t tot
 int32_t ctr_dot_interaction_bwd(const float* Z, const float* dR, int64_t dr_stride,
                                 int64_t batch, int32_t num_vectors, int32_t dim, int32_t compute,
                                 int32_t dz_dtype, void* dZ, void* stream) {
-  return interaction_bwd_common(Z, dR, dr_stride, batch, num_vectors, dim, compute, false,
-                                dz_dtype, dZ, stream, "ctr_dot_interaction_bwd");
+  return interaction_bwd_common(Z, dR, dr_stride, batch, num_vectors, dim, compute,
+                                ctr::kPairStrict, dz_dtype, dZ, stream, "ctr_dot_interaction_bwd");
 }
 
 int32_t ctr_dot_interaction_self_fwd(const float* Z, int64_t batch, int32_t num_vectors,
                                      int32_t dim, int32_t compute, float* R, int64_t r_stride,
                                      void* stream) {
-  return interaction_fwd_common(Z, batch, num_vectors, dim, compute, true, R, r_stride, stream,
-                                "ctr_dot_interaction_self_fwd");
+  return interaction_fwd_common(Z, batch, num_vectors, dim, compute, ctr::kPairSelf, R,
+                                r_stride, stream, "ctr_dot_interaction_self_fwd");
 }
 
 int32_t ctr_dot_interaction_self_bwd(const float* Z, const float* dR, int64_t dr_stride,
                                      int64_t batch, int32_t num_vectors, int32_t dim,
                                      int32_t compute, int32_t dz_dtype, void* dZ, void* stream) {
-  return interaction_bwd_common(Z, dR, dr_stride, batch, num_vectors, dim, compute, true,
-                                dz_dtype, dZ, stream, "ctr_dot_interaction_self_bwd");
+  return interaction_bwd_common(Z, dR, dr_stride, batch, num_vectors, dim, compute,
+                                ctr::kPairSelf, dz_dtype, dZ, stream,
+                                "ctr_dot_interaction_self_bwd");
+}
+
+int32_t ctr_dot_interaction_gram_fwd(const float* Z, int64_t batch, int32_t num_vectors,
+                                     int32_t dim, int32_t compute, float* R, int64_t r_stride,
+                                     void* stream) {
+  return interaction_fwd_common(Z, batch, num_vectors, dim, compute, ctr::kPairGram, R,
+                                r_stride, stream, "ctr_dot_interaction_gram_fwd");
+}
+
+int32_t ctr_dot_interaction_gram_bwd(const float* Z, const float* dR, int64_t dr_stride,
+                                     int64_t batch, int32_t num_vectors, int32_t dim,
+                                     int32_t compute, int32_t dz_dtype, void* dZ, void* stream) {
+  return interaction_bwd_common(Z, dR, dr_stride, batch, num_vectors, dim, compute,
+                                ctr::kPairGram, dz_dtype, dZ, stream,
+                                "ctr_dot_interaction_gram_bwd");
 }
 
 static int32_t check_fm(const float* Z, int64_t batch, int32_t F, int32_t dim, const float* a,

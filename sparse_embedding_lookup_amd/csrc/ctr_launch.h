@@ -83,13 +83,15 @@ hipError_t launch_dict_pool(const int64_t* values, int64_t nnz, const int64_t* o
                             int64_t hot_rows, const void* cold, int64_t cold_rows, int elt,
                             int dim, float* out, int64_t sb, int64_t st, hipStream_t s);
 
-// interaction.hip
-bool interaction_bf16_supported(int F, int dim, bool self);
-bool interaction_f32_supported(int F, int dim, bool self);
+// interaction.hip.  pairs: the pair set, kPairStrict (i > j), kPairSelf (i >= j) or
+// kPairGram (the whole F x F Gram matrix).
+constexpr int kPairStrict = 0, kPairSelf = 1, kPairGram = 2;
+bool interaction_bf16_supported(int F, int dim, int pairs);
+bool interaction_f32_supported(int F, int dim, int pairs);
 hipError_t launch_interaction_fwd(const float* Z, int64_t batch, int F, int dim, bool bf16,
-                                  bool self, float* R, int64_t r_stride, hipStream_t s);
+                                  int pairs, float* R, int64_t r_stride, hipStream_t s);
 hipError_t launch_interaction_bwd(const float* Z, const float* dR, int64_t dr_stride,
-                                  int64_t batch, int F, int dim, bool bf16, bool self,
+                                  int64_t batch, int F, int dim, bool bf16, int pairs,
                                   bool out_bf16, void* dZ, hipStream_t s);
 hipError_t launch_fm_fwd(const float* Z, int64_t batch, int F, int dim, float* out,
                          hipStream_t s);

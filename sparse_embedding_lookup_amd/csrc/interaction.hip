@@ -18,10 +18,16 @@
 //     fp32, or rounded to bf16 for a bf16 backward (half the bytes its consumer re-reads).
 // Both paths are memory-bound on the 8 TB/s HBM: the arithmetic intensity is 6-14 flop/B.
 //
-// Variants ("DHEN" notes, 3.1 and Solution 2):
-//   SELF: the pairs i >= j, self-dots included ("all inner products for i <= j"):
-//     P = F(F+1)/2 in row-major lower-triangle order (index i(i+1)/2 + j), and the gradient
-//     of <z_i, z_i> is 2 z_i.  Every kernel below takes SELF as a template parameter.
+// Variants ("DHEN" notes, 3.1, Solution 2 and 3.3):
+//   the pair set PS of every kernel below (a template parameter):
+//   kStrict  the pairs i > j (above);
+//   kSelf    the pairs i >= j, self-dots included ("all inner products for i <= j"):
+//            P = F(F+1)/2 in row-major lower-triangle order (index i(i+1)/2 + j), and the
+//            gradient of <z_i, z_i> is 2 z_i;
+//   kGram    the whole Gram matrix Z Z^T that a DCN-style layer takes (3.3, eq. (7)):
+//            P = F^2 in row-major order (index i F + j, both triangles: the dot of i > j is
+//            computed once and written twice), and dZ_i = sum_j (dG_ij + dG_ji) z_j with the
+//            two mirrored gradients added in binary32 first (the diagonal: 2 dG_ii).
 //   FM sum: per sample the sum of all pair dots by the squared-norm identity,
 //     out = 1/2 (||sum_i z_i||^2 - sum_i ||z_i||^2), O(F d) instead of O(F^2 d);
 //     dZ_i = dout * (sum_j z_j - z_i).
@@ -48,25 +54,58 @@ __device__ __forceinline__ int tri_index(int i, int j) {
   return i > j ? i * (i - 1) / 2 + j : j * (j - 1) / 2 + i;
 }
 
-// Pair counts and indices of the two pair sets: strict (i > j) or with self-dots (i >= j).
-template <bool SELF>
-__host__ __device__ __forceinline__ int num_pairs(int F) {
-  return SELF ? F * (F + 1) / 2 : F * (F - 1) / 2;
+// Pair sets: strict (i > j), with self-dots (i >= j), or the whole Gram matrix.
+constexpr int kStrict = kPairStrict, kSelf = kPairSelf, kGram = kPairGram;
+
+// Outputs per sample after the dense slot, and the dots computed per sample (the Gram
+// matrix computes the i >= j dots and writes the others as mirrors).
+template <int PS>
+__host__ __device__ constexpr int num_pairs(int F) {
+  return PS == kGram ? F * F : PS == kSelf ? F * (F + 1) / 2 : F * (F - 1) / 2;
 }
-template <bool SELF>
-__device__ __forceinline__ int pair_index(int i, int j) {     // requires i > j (i >= j: SELF)
-  return SELF ? i * (i + 1) / 2 + j : i * (i - 1) / 2 + j;
+template <int PS>
+__host__ __device__ constexpr int num_dots(int F) {
+  return PS == kStrict ? F * (F - 1) / 2 : F * (F + 1) / 2;
 }
-template <bool SELF>
+__host__ inline int num_pairs_of(int pairs, int F) {
+  return pairs == kGram ? num_pairs<kGram>(F) : pairs == kSelf ? num_pairs<kSelf>(F)
+                                                              : num_pairs<kStrict>(F);
+}
+// Index of the dot (i, j) among the computed dots (i > j; i >= j unless strict).
+template <int PS>
+__device__ __forceinline__ int pair_index(int i, int j) {
+  return PS != kStrict ? i * (i + 1) / 2 + j : i * (i - 1) / 2 + j;
+}
+template <int PS>
 __device__ __forceinline__ int sym_pair_index(int i, int j) {
-  return i >= j ? pair_index<SELF>(i, j) : pair_index<SELF>(j, i);
+  return i >= j ? pair_index<PS>(i, j) : pair_index<PS>(j, i);
 }
-// Row and column of pair index q.
-template <bool SELF>
+// Row and column of computed dot q.
+template <int PS>
 __device__ __forceinline__ void pair_of(int q, int* i, int* j) {
-  const int r = SELF ? tri_row(q) - 1 : tri_row(q);
+  const int r = PS != kStrict ? tri_row(q) - 1 : tri_row(q);
   *i = r;
-  *j = q - (SELF ? r * (r + 1) / 2 : r * (r - 1) / 2);
+  *j = q - (PS != kStrict ? r * (r + 1) / 2 : r * (r - 1) / 2);
+}
+// Stores the dot of (i, j) (i > j; i >= j unless strict) into a sample's output row o (the
+// pair part): once, or at (i, j) and (j, i) for the Gram matrix.
+template <int PS>
+__device__ __forceinline__ void store_dot(float* o, int F, int i, int j, float v) {
+  if constexpr (PS == kGram) {
+    o[i * F + j] = v;
+    if (i != j) o[j * F + i] = v;
+  } else {
+    o[pair_index<PS>(i, j)] = v;
+  }
+}
+// Entry (i, j) of the symmetric gradient matrix S with dZ = S Z, from a sample's pair
+// gradients g: the pair's gradient (i != j), twice the self-dot's (i == j, self set), zero
+// on the strict set's diagonal; for the Gram matrix dG_ij + dG_ji in binary32.
+template <int PS>
+__device__ __forceinline__ float s_entry(const float* g, int F, int i, int j) {
+  if constexpr (PS == kGram) return g[i * F + j] + g[j * F + i];
+  if (i == j) return PS == kSelf ? 2.0f * g[pair_index<kSelf>(i, i)] : 0.0f;
+  return g[sym_pair_index<PS>(i, j)];
 }
 
 // An empty asm that claims to change an offset: loads addressed through it stay where they
@@ -85,7 +124,7 @@ __device__ __forceinline__ bf16x8 pack_bf16x8(const float* x) {
 }
 
 // ------------------------------------------------------------------------- fp32 forward
-template <bool SELF>
+template <int PS>
 __global__ __launch_bounds__(kThreads) void interaction_fwd_f32_kernel(
     const float* __restrict__ Z, int64_t batch, int F, int dim, int spb,
     float* __restrict__ R, int64_t r_stride) {
@@ -100,7 +139,7 @@ __global__ __launch_bounds__(kThreads) void interaction_fwd_f32_kernel(
     zs[(s * F + i) * ld + c] = Z[(b0 + s) * per + r];
   }
   __syncthreads();
-  const int P = num_pairs<SELF>(F);
+  const int P = num_pairs<PS>(F);
   const int W = dim + P;
   for (int q = threadIdx.x; q < nb * W; q += kThreads) {
     const int s = q / W, e = q - s * W;
@@ -108,8 +147,15 @@ __global__ __launch_bounds__(kThreads) void interaction_fwd_f32_kernel(
     if (e < dim) {
       v = zs[(s * F) * ld + e];
     } else {
+      // the Gram matrix's (i, j) and (j, i) are the same fused multiply-add chain
+      // (multiplication commutes), so the two mirrors come out equal
       int i, j;
-      pair_of<SELF>(e - dim, &i, &j);
+      if constexpr (PS == kGram) {
+        i = (e - dim) / F;
+        j = (e - dim) - i * F;
+      } else {
+        pair_of<PS>(e - dim, &i, &j);
+      }
       const float* zi = zs + (s * F + i) * ld;
       const float* zj = zs + (s * F + j) * ld;
       float acc = 0.f;
@@ -121,13 +167,13 @@ __global__ __launch_bounds__(kThreads) void interaction_fwd_f32_kernel(
 }
 
 // ------------------------------------------------------------------------- fp32 backward
-template <bool SELF>
+template <int PS>
 __global__ __launch_bounds__(kThreads) void interaction_bwd_f32_kernel(
     const float* __restrict__ Z, const float* __restrict__ dR, int64_t dr_stride,
     int64_t batch, int F, int dim, int spb, float* __restrict__ dZ) {
   extern __shared__ float smem[];
   const int ld = dim + 1;
-  const int P = num_pairs<SELF>(F);
+  const int P = num_pairs<PS>(F);
   float* zs = smem;                       // [spb][F][ld]
   float* ps = smem + spb * F * ld;        // [spb][P]
   const int64_t b0 = (int64_t)blockIdx.x * spb;
@@ -150,11 +196,8 @@ __global__ __launch_bounds__(kThreads) void interaction_bwd_f32_kernel(
     const float* zc = zs + (s * F) * ld + c;
     const float* pp = ps + s * P;
     for (int j = 0; j < F; ++j) {
-      if (j == i) {
-        if (SELF) acc = __builtin_fmaf(2.0f * pp[pair_index<true>(i, i)], zc[j * ld], acc);
-        continue;
-      }
-      acc = __builtin_fmaf(pp[sym_pair_index<SELF>(i, j)], zc[j * ld], acc);
+      if (PS == kStrict && j == i) continue;
+      acc = __builtin_fmaf(s_entry<PS>(pp, F, i, j), zc[j * ld], acc);
     }
     dZ[(b0 + s) * per + r] = acc;
   }
@@ -171,13 +214,14 @@ constexpr int kLaneThreads = 64;
 // LDS (dynamic: samples x P x (L + 1) floats), and after one barrier lane l sums pairs
 // l, l + L, ... over the sample's L partials.  For FMAX = 32 (up to 496 pairs) the partials
 // are summed with xor shuffles instead.
-template <int FMAX, int L, bool SELF>
+template <int FMAX, int L, int PS>
 __global__ __launch_bounds__(kLaneThreads) void interaction_fwd_lanes_kernel(
     const float* __restrict__ Z, int64_t batch, int F, float* __restrict__ R, int64_t r_stride) {
   constexpr int kDim = 4 * L;
   constexpr bool kLds = FMAX <= 16;
-  extern __shared__ float part[];              // [64 / L][P][L + 1] when kLds
-  const int P = num_pairs<SELF>(F);
+  constexpr bool kSelfDots = PS != kStrict;
+  extern __shared__ float part[];              // [64 / L][dots][L + 1] when kLds
+  const int P = num_dots<PS>(F);
   const int lane = threadIdx.x % L;
   const int64_t b = (int64_t)blockIdx.x * (kLaneThreads / L) + threadIdx.x / L;
   const bool ok = b < batch;
@@ -197,9 +241,9 @@ __global__ __launch_bounds__(kLaneThreads) void interaction_fwd_lanes_kernel(
   float* ps = part + (int64_t)sl * P * (L + 1);
   int p = 0;
 #pragma unroll
-  for (int i = SELF ? 0 : 1; i < FMAX; ++i) {
+  for (int i = kSelfDots ? 0 : 1; i < FMAX; ++i) {
 #pragma unroll
-    for (int j = 0; j < (SELF ? i + 1 : i); ++j, ++p) {
+    for (int j = 0; j < (kSelfDots ? i + 1 : i); ++j, ++p) {
       if (i < F) {
         float v = z[i].x * z[j].x;
         v = __builtin_fmaf(z[i].y, z[j].y, v);
@@ -210,7 +254,7 @@ __global__ __launch_bounds__(kLaneThreads) void interaction_fwd_lanes_kernel(
         } else {
 #pragma unroll
           for (int o = L / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, L);
-          if (ok && lane == p % L) rb[kDim + p] = v;
+          if (ok && lane == p % L) store_dot<PS>(rb + kDim, F, i, j, v);
         }
       }
     }
@@ -222,22 +266,24 @@ __global__ __launch_bounds__(kLaneThreads) void interaction_fwd_lanes_kernel(
       float v = 0.f;
 #pragma unroll
       for (int l = 0; l < L; ++l) v += row[l];
-      if (ok) rb[kDim + q] = v;
+      int i, j;
+      pair_of<PS>(q, &i, &j);
+      if (ok) store_dot<PS>(rb + kDim, F, i, j, v);
     }
   }
 }
 
 // Backward: dZ_i = sum_{j != i} dP(i, j) z_j (+ dR_dense for i = 0), one output slice at a
 // time; the sample's pair gradients are staged in LDS and read as broadcasts.
-template <int FMAX, int L, bool SELF>
+template <int FMAX, int L, int PS>
 __global__ __launch_bounds__(kLaneThreads) void interaction_bwd_lanes_kernel(
     const float* __restrict__ Z, const float* __restrict__ dR, int64_t dr_stride, int64_t batch,
     int F, float* __restrict__ dZ) {
   constexpr int kDim = 4 * L;
   constexpr int kS = kLaneThreads / L;                     // samples per block
-  constexpr int kPmax = SELF ? FMAX * (FMAX + 1) / 2 : FMAX * (FMAX - 1) / 2;
+  constexpr int kPmax = num_pairs<PS>(FMAX);
   __shared__ float dp[kS][kPmax];
-  const int P = num_pairs<SELF>(F);
+  const int P = num_pairs<PS>(F);
   const int64_t b0 = (int64_t)blockIdx.x * kS;
   for (int q = threadIdx.x; q < kS * P; q += kLaneThreads) {
     const int s = q / P, r = q - s * P;
@@ -261,9 +307,8 @@ __global__ __launch_bounds__(kLaneThreads) void interaction_bwd_lanes_kernel(
       float4 acc = i == 0 ? dense : make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
       for (int j = 0; j < FMAX; ++j) {
-        if ((SELF || j != i) && j < F) {
-          const float g = j == i ? 2.0f * dp[sl][pair_index<true>(i, i)]
-                                 : dp[sl][sym_pair_index<SELF>(i, j)];
+        if ((PS != kStrict || j != i) && j < F) {
+          const float g = s_entry<PS>(dp[sl], F, i, j);
           acc.x = __builtin_fmaf(g, z[j].x, acc.x);
           acc.y = __builtin_fmaf(g, z[j].y, acc.y);
           acc.z = __builtin_fmaf(g, z[j].z, acc.z);
@@ -294,11 +339,13 @@ __global__ __launch_bounds__(kLaneThreads) void interaction_bwd_lanes_kernel(
     else { CTR_LANES_L(32, __VA_ARGS__) }                                    \
   } while (0)
 
-bool lanes_shape(int F, int dim, bool self) {
+bool lanes_shape(int F, int dim, int pairs) {
   const int L = dim / 4;
   if (!(F <= 32 && dim % 4 == 0 && L >= 1 && L <= 64 && (L & (L - 1)) == 0)) return false;
+  // the Gram matrix's F^2 gradients per sample: the backward's LDS for F <= 16 only
+  if (pairs == kGram && F > 16) return false;
   // the forward's LDS partials (F <= 16) must fit one block's 64 KiB
-  const int P = self ? F * (F + 1) / 2 : F * (F - 1) / 2;
+  const int P = pairs == kStrict ? F * (F - 1) / 2 : F * (F + 1) / 2;
   return F > 16 || (size_t)(kLaneThreads / L) * P * (L + 1) * sizeof(float) <= 65536;
 }
 
@@ -328,7 +375,7 @@ __device__ __forceinline__ void load_row_block(const float* __restrict__ zb, int
 
 // FB: 32-row blocks covering F (F <= 32*FB); KS: dim / 16 (k-steps of 16).  All FB row
 // blocks of fragments stay in registers.
-template <int FB, int KS, bool SELF>
+template <int FB, int KS, int PS>
 __global__ __launch_bounds__(kThreads) void interaction_fwd_mfma_kernel(
     const float* __restrict__ Z, int64_t batch, int F, float* __restrict__ R, int64_t r_stride) {
   constexpr int dim = KS * 16;
@@ -351,7 +398,7 @@ __global__ __launch_bounds__(kThreads) void interaction_fwd_mfma_kernel(
     if (32 * I >= F) break;
 #pragma unroll
     for (int J = 0; J <= I; ++J) {
-      if (!SELF && J == I && F - 32 * I < 2) break;  // no pair i > j inside this tile
+      if (PS == kStrict && J == I && F - 32 * I < 2) break;  // no pair i > j inside this tile
       f32x16 acc;
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[v] = 0.f;
@@ -363,7 +410,7 @@ __global__ __launch_bounds__(kThreads) void interaction_fwd_mfma_kernel(
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int i = 32 * I + 8 * (v >> 2) + 4 * kg + (v & 3);
-        if (i < F && (SELF ? j <= i : j < i)) rb[dim + pair_index<SELF>(i, j)] = acc[v];
+        if (i < F && (PS != kStrict ? j <= i : j < i)) store_dot<PS>(rb + dim, F, i, j, acc[v]);
       }
     }
   }
@@ -376,7 +423,7 @@ __global__ __launch_bounds__(kThreads) void interaction_fwd_mfma_kernel(
 // and each 32-column slab of Z (B operand, re-read per row block from L1/L2), 2*FB MFMAs give
 // a 32x32 block of dZ.
 // OUTB: dZ is stored as bf16 (nearest-even of the fp32 accumulator) instead of fp32.
-template <int FB, int KS, bool SELF, bool OUTB>
+template <int FB, int KS, int PS, bool OUTB>
 __global__ __launch_bounds__(kThreads) void interaction_bwd_mfma_kernel(
     const float* __restrict__ Z, const float* __restrict__ dR, int64_t dr_stride,
     int64_t batch, int F, int wpb, void* __restrict__ dZ) {
@@ -385,13 +432,22 @@ __global__ __launch_bounds__(kThreads) void interaction_bwd_mfma_kernel(
   extern __shared__ __align__(16) unsigned char sp_raw[];
   const int lane = threadIdx.x & 63;
   const int wv = threadIdx.x >> 6;
-  const int P = num_pairs<SELF>(F);
+  const int P = num_pairs<PS>(F);
   const int64_t b = (int64_t)blockIdx.x * wpb + wv;
   const bool live = wv < wpb && b < batch;
   // slot P holds 0: the padding (and the diagonal); P + 2 slots keep 4-byte alignment
   __bf16* sp = reinterpret_cast<__bf16*>(sp_raw) + wv * (P + 2);
   if (live) {
-    for (int q = lane; q < P; q += 64) sp[q] = (__bf16)dR[b * dr_stride + dim + q];
+    const float* g = dR + b * dr_stride + dim;
+    if constexpr (PS == kGram) {
+      // S itself: dG_ij + dG_ji in binary32, then rounded to bf16 once
+      for (int q = lane; q < P; q += 64) {
+        const int i = q / F, j = q - (q / F) * F;
+        sp[q] = (__bf16)(g[i * F + j] + g[j * F + i]);
+      }
+    } else {
+      for (int q = lane; q < P; q += 64) sp[q] = (__bf16)g[q];
+    }
     if (lane == 0) sp[P] = (__bf16)0.f;
   }
   __syncthreads();
@@ -420,10 +476,14 @@ __global__ __launch_bounds__(kThreads) void interaction_bwd_mfma_kernel(
         const int j = 16 * s + 8 * kgx + e;
         const int vj = (int)((unsigned)(j - F) >> 31);           // 1 if j < F
         const int ne = (int)((0u - (unsigned)(i ^ j)) >> 31);    // 1 if i != j
-        const int ok = vi & vj & (SELF ? 1 : ne);
-        const int q = ok * (SELF ? sym_pair_index<true>(i, j) : tri_index(i, j)) + (1 - ok) * P;
+        const int ok = vi & vj & (PS != kStrict ? 1 : ne);
+        const int q = ok * (PS == kGram   ? i * F + j
+                            : PS == kSelf ? sym_pair_index<kSelf>(i, j)
+                                          : tri_index(i, j)) +
+                      (1 - ok) * P;
         // d<z_i, z_i>/dz_i = 2 z_i: the diagonal of S carries twice the self-dot gradient
-        af[s][e] = SELF ? (__bf16)((float)sp[q] * (float)(2 - ne)) : sp[q];
+        // (the Gram matrix's S already holds dG_ii + dG_ii)
+        af[s][e] = PS == kSelf ? (__bf16)((float)sp[q] * (float)(2 - ne)) : sp[q];
       }
     }
 #pragma unroll 1
@@ -543,8 +603,8 @@ __global__ __launch_bounds__(kThreads) void fm_bwd_kernel(const float* __restric
 
 // Samples per block of the fp32 kernels: as many as 32 KiB of LDS holds, but no more than
 // keeps about 1024 blocks in flight (four per CU), so small batches still fill the chip.
-int f32_spb(int64_t batch, int F, int dim, bool bwd, bool self) {
-  const int per = (F * (dim + 1) + (bwd ? (self ? num_pairs<true>(F) : num_pairs<false>(F)) : 0)) * 4;
+int f32_spb(int64_t batch, int F, int dim, bool bwd, int pairs) {
+  const int per = (F * (dim + 1) + (bwd ? num_pairs_of(pairs, F) : 0)) * 4;
   int64_t spb = 32768 / per;
   const int64_t fill = batch / 1024;
   if (spb > fill) spb = fill;
@@ -555,17 +615,17 @@ int f32_spb(int64_t batch, int F, int dim, bool bwd, bool self) {
 
 }  // namespace
 
-bool interaction_bf16_supported(int F, int dim, bool self) {
+bool interaction_bf16_supported(int F, int dim, int pairs) {
   if (dim % 16 != 0 || F > 128) return false;
   const int FB = (F + 31) / 32, KS = dim / 16;
   if (!(KS == 1 || KS == 2 || KS == 4 || KS == 8)) return false;
   if (FB * KS > 32) return false;                       // register budget of the forward
-  const int P = self ? num_pairs<true>(F) : num_pairs<false>(F);
-  return (P + 1) * 4 <= 65536;
+  // one wave's bf16 gradients in LDS
+  return ((size_t)num_pairs_of(pairs, F) + 2) * 2 <= 65536;
 }
 
-bool interaction_f32_supported(int F, int dim, bool self) {
-  const int per = (F * (dim + 1) + (self ? num_pairs<true>(F) : num_pairs<false>(F))) * 4;
+bool interaction_f32_supported(int F, int dim, int pairs) {
+  const int per = (F * (dim + 1) + num_pairs_of(pairs, F)) * 4;
   return per <= 65536;
 }
 
@@ -579,59 +639,69 @@ bool interaction_f32_supported(int F, int dim, bool self) {
 
 namespace {
 
-template <bool SELF>
+template <int PS>
 hipError_t interaction_fwd(const float* Z, int64_t batch, int F, int dim, bool bf16, float* R,
                            int64_t r_stride, hipStream_t s) {
   if (batch == 0) return hipSuccess;
-  const int P = num_pairs<SELF>(F);
   if (!bf16) {
-    if (lanes_shape(F, dim, SELF)) {
+    if (lanes_shape(F, dim, PS)) {
+      const int P = num_dots<PS>(F);        // the forward's LDS partials
       const int L_ = dim / 4;
       const int64_t blocks = (batch * L_ + kLaneThreads - 1) / kLaneThreads;
       const size_t lds = F <= 16 ? (size_t)(kLaneThreads / L_) * P * (L_ + 1) * sizeof(float) : 0;
-      CTR_LANES(F, L_, interaction_fwd_lanes_kernel<FMAX, L, SELF><<<(unsigned)blocks, kLaneThreads, lds, s>>>(
+      CTR_LANES(F, L_, interaction_fwd_lanes_kernel<FMAX, L, PS><<<(unsigned)blocks, kLaneThreads, lds, s>>>(
                            Z, batch, F, R, r_stride));
       return hipGetLastError();
     }
-    const int spb = f32_spb(batch, F, dim, false, SELF);
+    const int spb = f32_spb(batch, F, dim, false, PS);
     const size_t lds = (size_t)spb * F * (dim + 1) * sizeof(float);
     const int64_t blocks = (batch + spb - 1) / spb;
-    interaction_fwd_f32_kernel<SELF><<<(unsigned)blocks, kThreads, lds, s>>>(Z, batch, F, dim, spb,
-                                                                             R, r_stride);
+    interaction_fwd_f32_kernel<PS><<<(unsigned)blocks, kThreads, lds, s>>>(Z, batch, F, dim, spb,
+                                                                           R, r_stride);
     return hipGetLastError();
   }
   const int FB = (F + 31) / 32, KS = dim / 16;
   const int64_t blocks = (batch + 3) / 4;
   CTR_FB_DISPATCH(FB, {
     switch (KS) {
-      case 1: interaction_fwd_mfma_kernel<FB, 1, SELF><<<(unsigned)blocks, kThreads, 0, s>>>(Z, batch, F, R, r_stride); break;
-      case 2: interaction_fwd_mfma_kernel<FB, 2, SELF><<<(unsigned)blocks, kThreads, 0, s>>>(Z, batch, F, R, r_stride); break;
-      case 4: interaction_fwd_mfma_kernel<FB, 4, SELF><<<(unsigned)blocks, kThreads, 0, s>>>(Z, batch, F, R, r_stride); break;
-      default: interaction_fwd_mfma_kernel<FB, 8, SELF><<<(unsigned)blocks, kThreads, 0, s>>>(Z, batch, F, R, r_stride); break;
+      case 1: interaction_fwd_mfma_kernel<FB, 1, PS><<<(unsigned)blocks, kThreads, 0, s>>>(Z, batch, F, R, r_stride); break;
+      case 2: interaction_fwd_mfma_kernel<FB, 2, PS><<<(unsigned)blocks, kThreads, 0, s>>>(Z, batch, F, R, r_stride); break;
+      case 4: interaction_fwd_mfma_kernel<FB, 4, PS><<<(unsigned)blocks, kThreads, 0, s>>>(Z, batch, F, R, r_stride); break;
+      default: interaction_fwd_mfma_kernel<FB, 8, PS><<<(unsigned)blocks, kThreads, 0, s>>>(Z, batch, F, R, r_stride); break;
     }
   });
   return hipGetLastError();
 }
 
-template <bool SELF>
+template <int PS>
 hipError_t interaction_bwd(const float* Z, const float* dR, int64_t dr_stride, int64_t batch,
                            int F, int dim, bool bf16, bool out_bf16, void* dZv, hipStream_t s) {
   if (batch == 0) return hipSuccess;
-  const int P = num_pairs<SELF>(F);
+  const int P = num_pairs<PS>(F);
   float* dZ = static_cast<float*>(dZv);
   if (!bf16) {
-    if (lanes_shape(F, dim, SELF)) {
+    if (lanes_shape(F, dim, PS)) {
       const int L_ = dim / 4;
       const int64_t blocks = (batch * L_ + kLaneThreads - 1) / kLaneThreads;
-      CTR_LANES(F, L_, interaction_bwd_lanes_kernel<FMAX, L, SELF><<<(unsigned)blocks, kLaneThreads, 0, s>>>(
-                           Z, dR, dr_stride, batch, F, dZ));
+      if constexpr (PS == kGram) {          // F <= 16 (lanes_shape): F^2 gradients in LDS
+        if (F <= 8) {
+          CTR_LANES_L(8, interaction_bwd_lanes_kernel<FMAX, L, PS><<<(unsigned)blocks, kLaneThreads, 0, s>>>(
+                             Z, dR, dr_stride, batch, F, dZ));
+        } else {
+          CTR_LANES_L(16, interaction_bwd_lanes_kernel<FMAX, L, PS><<<(unsigned)blocks, kLaneThreads, 0, s>>>(
+                              Z, dR, dr_stride, batch, F, dZ));
+        }
+      } else {
+        CTR_LANES(F, L_, interaction_bwd_lanes_kernel<FMAX, L, PS><<<(unsigned)blocks, kLaneThreads, 0, s>>>(
+                             Z, dR, dr_stride, batch, F, dZ));
+      }
       return hipGetLastError();
     }
-    const int spb = f32_spb(batch, F, dim, true, SELF);
+    const int spb = f32_spb(batch, F, dim, true, PS);
     const size_t lds = (size_t)spb * (F * (dim + 1) + P) * sizeof(float);
     const int64_t blocks = (batch + spb - 1) / spb;
-    interaction_bwd_f32_kernel<SELF><<<(unsigned)blocks, kThreads, lds, s>>>(Z, dR, dr_stride,
-                                                                             batch, F, dim, spb, dZ);
+    interaction_bwd_f32_kernel<PS><<<(unsigned)blocks, kThreads, lds, s>>>(Z, dR, dr_stride,
+                                                                           batch, F, dim, spb, dZ);
     return hipGetLastError();
   }
   const int FB = (F + 31) / 32;
@@ -644,10 +714,10 @@ hipError_t interaction_bwd(const float* Z, const float* dR, int64_t dr_stride, i
 #define CTR_BWD_MFMA(KS_)                                                                      \
   do {                                                                                         \
     if (out_bf16)                                                                              \
-      interaction_bwd_mfma_kernel<FB, KS_, SELF, true><<<(unsigned)blocks, kThreads, lds, s>>>( \
+      interaction_bwd_mfma_kernel<FB, KS_, PS, true><<<(unsigned)blocks, kThreads, lds, s>>>( \
           Z, dR, dr_stride, batch, F, wpb, dZv);                                               \
     else                                                                                       \
-      interaction_bwd_mfma_kernel<FB, KS_, SELF, false><<<(unsigned)blocks, kThreads, lds, s>>>( \
+      interaction_bwd_mfma_kernel<FB, KS_, PS, false><<<(unsigned)blocks, kThreads, lds, s>>>( \
           Z, dR, dr_stride, batch, F, wpb, dZv);                                               \
   } while (0)
   CTR_FB_DISPATCH(FB, {
@@ -665,16 +735,20 @@ hipError_t interaction_bwd(const float* Z, const float* dR, int64_t dr_stride, i
 }  // namespace
 
 hipError_t launch_interaction_fwd(const float* Z, int64_t batch, int F, int dim, bool bf16,
-                                  bool self, float* R, int64_t r_stride, hipStream_t s) {
-  return self ? interaction_fwd<true>(Z, batch, F, dim, bf16, R, r_stride, s)
-              : interaction_fwd<false>(Z, batch, F, dim, bf16, R, r_stride, s);
+                                  int pairs, float* R, int64_t r_stride, hipStream_t s) {
+  if (pairs == kGram) return interaction_fwd<kGram>(Z, batch, F, dim, bf16, R, r_stride, s);
+  if (pairs == kSelf) return interaction_fwd<kSelf>(Z, batch, F, dim, bf16, R, r_stride, s);
+  return interaction_fwd<kStrict>(Z, batch, F, dim, bf16, R, r_stride, s);
 }
 
 hipError_t launch_interaction_bwd(const float* Z, const float* dR, int64_t dr_stride,
-                                  int64_t batch, int F, int dim, bool bf16, bool self,
+                                  int64_t batch, int F, int dim, bool bf16, int pairs,
                                   bool out_bf16, void* dZ, hipStream_t s) {
-  return self ? interaction_bwd<true>(Z, dR, dr_stride, batch, F, dim, bf16, out_bf16, dZ, s)
-              : interaction_bwd<false>(Z, dR, dr_stride, batch, F, dim, bf16, out_bf16, dZ, s);
+  if (pairs == kGram)
+    return interaction_bwd<kGram>(Z, dR, dr_stride, batch, F, dim, bf16, out_bf16, dZ, s);
+  if (pairs == kSelf)
+    return interaction_bwd<kSelf>(Z, dR, dr_stride, batch, F, dim, bf16, out_bf16, dZ, s);
+  return interaction_bwd<kStrict>(Z, dR, dr_stride, batch, F, dim, bf16, out_bf16, dZ, s);
 }
 
 hipError_t launch_fm_fwd(const float* Z, int64_t batch, int F, int dim, float* out,

@@ -33,7 +33,8 @@ EXPORTED = [
     "ctr_step_run_deep",
     "ctr_dense_fwd", "ctr_dense_bwd_sgd", "ctr_logistic_ne", "ctr_embbag_interaction_fwd",
     "ctr_embbag_bwd_sgd_noalloc", "ctr_embbag_bwd_noalloc_scratch_bytes",
-    "ctr_noalloc_scratch_capacity",
+    "ctr_noalloc_scratch_capacity", "ctr_dot_interaction_gram_fwd",
+    "ctr_dot_interaction_gram_bwd",
 ]
 
 CTR_STEP_POOLED_INTERACTION, CTR_STEP_BATCH_MATRIX = 0, 1
@@ -101,6 +102,8 @@ def load() -> ctypes.CDLL:
         "ctr_sr_step_seed": (u64, [u64, i64]),
         "ctr_dot_interaction_self_fwd": (i32, [P, i64, i32, i32, i32, P, i64, P]),
         "ctr_dot_interaction_self_bwd": (i32, [P, P, i64, i64, i32, i32, i32, i32, P, P]),
+        "ctr_dot_interaction_gram_fwd": (i32, [P, i64, i32, i32, i32, P, i64, P]),
+        "ctr_dot_interaction_gram_bwd": (i32, [P, P, i64, i64, i32, i32, i32, i32, P, P]),
         "ctr_fm_interaction_fwd": (i32, [P, i64, i32, i32, P, P]),
         "ctr_fm_interaction_bwd": (i32, [P, P, i64, i32, i32, P, P]),
         "ctr_embbag_bwd_sgd_noalloc": (i32, [P, i32, i64, i64, P, i64, i32, i64, P, P, P, i32,
@@ -433,6 +436,29 @@ def ctr_dot_interaction_self_bwd(Z: torch.Tensor, dR: torch.Tensor, compute: int
         dZ = torch.empty_like(Z)
     args = (_ptr(Z), _ptr(dR), dR.stride(0), B, F, d, compute, _dtype_code(dZ), _ptr(dZ))
     return _run("ctr_dot_interaction_self_bwd", args, stream, prepare, dZ)
+
+
+def ctr_dot_interaction_gram_fwd(Z: torch.Tensor, compute: int = CTR_F32,
+                                 R: Optional[torch.Tensor] = None, stream=None,
+                                 prepare: bool = False):
+    """The whole Gram matrix, P = F^2 row-major after the dense slot: R = [dense | Z Z^T]."""
+    B, F, d = Z.shape
+    if R is None:
+        R = torch.empty((B, d + F * F), dtype=torch.float32, device=Z.device)
+    args = (_ptr(Z), B, F, d, compute, _ptr(R), R.stride(0))
+    return _run("ctr_dot_interaction_gram_fwd", args, stream, prepare, R)
+
+
+def ctr_dot_interaction_gram_bwd(Z: torch.Tensor, dR: torch.Tensor, compute: int = CTR_F32,
+                                 dZ: Optional[torch.Tensor] = None, stream=None,
+                                 prepare: bool = False):
+    """dZ_i = sum_j (dG_ij + dG_ji) z_j (+ dense on slot 0); fp32, or bf16 when ``dZ`` is a
+    bf16 tensor (compute must be CTR_BF16)."""
+    B, F, d = Z.shape
+    if dZ is None:
+        dZ = torch.empty_like(Z)
+    args = (_ptr(Z), _ptr(dR), dR.stride(0), B, F, d, compute, _dtype_code(dZ), _ptr(dZ))
+    return _run("ctr_dot_interaction_gram_bwd", args, stream, prepare, dZ)
 
 
 def ctr_fm_interaction_fwd(Z: torch.Tensor, out: Optional[torch.Tensor] = None, stream=None,

@@ -256,6 +256,17 @@ def test_interaction_variant_bad_args():
     b = lib.ctr_dot_interaction_self_bwd
     assert b(FAKE, None, 31, 10, 5, 16, ctr.CTR_F32, ctr.CTR_F32, FAKE, None) == \
         ctr.CTR_ERR_INVALID_ARGUMENT
+    # the Gram matrix: F^2 entries after the dense slot, F >= 1
+    g = lib.ctr_dot_interaction_gram_fwd
+    assert g(FAKE, 10, 5, 16, ctr.CTR_F32, FAKE, 16 + 24, None) == ctr.CTR_ERR_INVALID_ARGUMENT
+    assert g(FAKE, 10, 0, 16, ctr.CTR_F32, FAKE, 100, None) == ctr.CTR_ERR_INVALID_ARGUMENT
+    assert g(FAKE, 10, 5000, 16, ctr.CTR_F32, FAKE, 1 << 26, None) == ctr.CTR_ERR_UNSUPPORTED
+    assert g(None, 0, 5, 16, ctr.CTR_F32, None, 16 + 25, None) == ctr.CTR_OK      # empty batch
+    gb = lib.ctr_dot_interaction_gram_bwd
+    assert gb(FAKE, None, 41, 10, 5, 16, ctr.CTR_F32, ctr.CTR_F32, FAKE, None) == \
+        ctr.CTR_ERR_INVALID_ARGUMENT
+    assert gb(FAKE, FAKE, 41, 10, 5, 16, ctr.CTR_F32, ctr.CTR_BF16, FAKE, None) == \
+        ctr.CTR_ERR_UNSUPPORTED
     assert lib.ctr_fm_interaction_fwd(FAKE, 10, 0, 16, FAKE, None) == \
         ctr.CTR_ERR_INVALID_ARGUMENT
     assert lib.ctr_fm_interaction_bwd(FAKE, None, 10, 3, 16, FAKE, None) == \

@@ -1,5 +1,6 @@
 """Interaction variants on the GPU through the C ABI, against the oracle ("DHEN" notes, 3.1:
-the pair set with self-dots; Solution 2: the FM sum by the squared-norm identity).
+the pair set with self-dots; Solution 2: the FM sum by the squared-norm identity; 3.3,
+eq. (7): the whole Gram matrix).
 
 The self-dot cases span the three arithmetic paths: the fp32 lane kernels (including a
 shape whose LDS partials no longer fit, which falls back), the LDS-staged fp32 kernels, and
@@ -72,6 +73,62 @@ def test_self_strided_output_and_strict_unchanged():
     # the strict entry point still writes F(F-1)/2 pairs
     Rs = host(ctr.ctr_dot_interaction_fwd(dev(Z), ctr.CTR_F32))
     assert Rs.shape == (B, d + F * (F - 1) // 2)
+
+
+# ----------------------------------------------------------------------------- Gram matrix
+# "DHEN" notes, 3.3, eq. (7): the whole F x F Gram matrix.  Shapes cover the fp32 lane
+# kernels (F <= 16, dim = 4L), the LDS-staged fp32 kernels (F above 16, other dims), and
+# bf16 on matrix cores over one to four 32-row blocks.
+GRAM_CASES = [
+    ("f32", 128, 5, 16), ("f32", 300, 16, 4), ("f32", 77, 1, 8), ("f32", 33, 27, 128),
+    ("f32", 19, 17, 48), ("f32", 64, 9, 256),
+    ("bf16", 100, 27, 128), ("bf16", 67, 65, 128), ("bf16", 40, 5, 16), ("bf16", 9, 1, 32),
+    ("bf16", 13, 100, 64),
+]
+
+
+@pytest.mark.parametrize("compute,B,F,d", GRAM_CASES)
+def test_gram_fwd_matches_oracle(compute, B, F, d):
+    say("interaction_gram_fwd", compute, B, F, d)
+    Z, _ = _inputs(B, F, d, 1, 21)
+    code = ctr.CTR_BF16 if compute == "bf16" else ctr.CTR_F32
+    R = host(ctr.ctr_dot_interaction_gram_fwd(dev(Z), code))
+    want, mag = orc.interaction_gram_fwd(Z.astype(np.float64), bf16=compute == "bf16")
+    assert_close(R, want, mag, gamma(d), "gram fwd")
+    np.testing.assert_array_equal(R[:, :d], Z[:, 0, :])
+    G = R[:, d:].reshape(B, F, F)
+    np.testing.assert_array_equal(G, np.transpose(G, (0, 2, 1)))     # one dot, two places
+
+
+@pytest.mark.parametrize("compute,B,F,d", GRAM_CASES)
+def test_gram_bwd_matches_oracle(compute, B, F, d):
+    say("interaction_gram_bwd", compute, B, F, d)
+    Z, dR = _inputs(B, F, d, d + F * F, 22)
+    code = ctr.CTR_BF16 if compute == "bf16" else ctr.CTR_F32
+    dZ = host(ctr.ctr_dot_interaction_gram_bwd(dev(Z), dev(dR), code))
+    want, mag = orc.interaction_gram_bwd(Z.astype(np.float64), dR.astype(np.float64),
+                                         bf16=compute == "bf16")
+    # fp32: the binary32 sum S_ij, F fused multiply-adds and the dense gradient; bf16: the
+    # same S on both sides, F products exact in fp32 and the dense gradient
+    assert_close(dZ, want, mag, gamma(F + 2 if compute == "f32" else F + 1), "gram bwd")
+    if compute == "bf16":
+        dZb = torch.empty((B, F, d), dtype=torch.bfloat16, device=DEV)
+        ctr.ctr_dot_interaction_gram_bwd(dev(Z), dev(dR), code, dZb)
+        np.testing.assert_array_equal(host(dZb), host(torch.from_numpy(dZ).to(torch.bfloat16)))
+
+
+def test_gram_strided_output_and_bad_stride():
+    B, F, d = 40, 6, 32
+    Z, _ = _inputs(B, F, d, 1, 23)
+    big = torch.full((B, d + F * F + 5), -3.0, device=DEV)
+    ctr.ctr_dot_interaction_gram_fwd(dev(Z), ctr.CTR_F32, big)
+    got = host(big)
+    want, mag = orc.interaction_gram_fwd(Z.astype(np.float64))
+    assert_close(got[:, :d + F * F], want, mag, gamma(d), "strided gram R")
+    assert np.all(got[:, d + F * F:] == -3.0)
+    small = torch.empty((B, d + F * F - 1), device=DEV)
+    with pytest.raises(ctr.CtrError):
+        ctr.ctr_dot_interaction_gram_fwd(dev(Z), ctr.CTR_F32, small)
 
 
 FM_CASES = [(128, 5, 16), (2048, 9, 64), (77, 27, 128), (33, 1, 8), (50, 65, 128),
