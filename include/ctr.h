@@ -133,12 +133,19 @@ int32_t ctr_gather_rows(const void* table, int32_t dtype, int64_t total_rows, in
  * Duplicates count with multiplicity; an empty bag writes zeros.  out_stride_* are in
  * floats and multiples of 4, so the pooled vectors can go straight into Z[b, 1 + t, :].
  * indices: int32 or int64 [nnz]; offsets: int64 [num_tables*batch + 1].
+ * A bag's rows are added in occurrence order in pieces of at most a few hundred, and the
+ * pieces joined in order, except in a bag of more than 4096 occurrences: that one is summed
+ * in chunks of 4096 occurrences spread over the whole GPU (each chunk over the lane groups of
+ * a block, joined pairwise) and the chunks' sums are added by a fixed pairwise tree, so the
+ * rounding depth grows with the logarithm of the bag's length.  Workspace (two-call query,
+ * 16-byte aligned, one call at a time): the chunks' partial sums, 256 bytes when nnz <= 4096.
  */
 int32_t ctr_embbag_fwd(const void* table, int32_t dtype, int64_t total_rows, int32_t dim,
                        const int64_t* row_base, int32_t num_tables,
                        const void* indices, int32_t index_type, int64_t nnz,
                        const int64_t* offsets, int64_t batch,
-                       float* out, int64_t out_stride_b, int64_t out_stride_t, void* stream);
+                       float* out, int64_t out_stride_b, int64_t out_stride_t,
+                       void* workspace, size_t* workspace_bytes, void* stream);
 
 /*
  * ctr_embbag_bwd -- chain rule of the sum pooling, reduced per distinct row ([TN]
@@ -489,6 +496,8 @@ typedef struct {
   int32_t mark_stage;             /* CTR_MARK_POOLING (0) or CTR_MARK_BACKWARD (1) */
   int64_t max_table_rows;         /* pooled step: rows of the largest table, or 0 (see
                                      ctr_unique_ids) */
+  void* ws_pool;                  /* the pooling's workspace (ctr_embbag_fwd's query) */
+  size_t ws_pool_bytes;
 } ctr_step_t;
 
 /*

@@ -181,10 +181,22 @@ int32_t ctr_gather_rows(const void* table, int32_t dtype, int64_t total_rows, in
 int32_t ctr_embbag_fwd(const void* table, int32_t dtype, int64_t total_rows, int32_t dim,
                        const int64_t* row_base, int32_t num_tables, const void* indices,
                        int32_t index_type, int64_t nnz, const int64_t* offsets, int64_t batch,
-                       float* out, int64_t out_stride_b, int64_t out_stride_t, void* stream) {
+                       float* out, int64_t out_stride_b, int64_t out_stride_t, void* workspace,
+                       size_t* workspace_bytes, void* stream) {
   g_msg[0] = 0;
+  if (!workspace_bytes) return fail(CTR_ERR_INVALID_ARGUMENT, "workspace_bytes is NULL");
+  if (nnz < 0 || nnz > kMaxElems) return fail(CTR_ERR_INVALID_ARGUMENT, "bad nnz");
+  if (dim <= 0 || dim > 4096) return fail(CTR_ERR_INVALID_ARGUMENT, "bad dim %d", dim);
+  const size_t need = ctr::embbag_fwd_workspace_bytes(nnz, dim);
+  if (!workspace) {                       // the query needs only nnz and dim
+    *workspace_bytes = need;
+    return CTR_OK;
+  }
   int32_t st = check_table(table, dtype, total_rows, dim);
   if (st) return st;
+  if (*workspace_bytes < need)
+    return fail(CTR_ERR_WORKSPACE_TOO_SMALL, "workspace %zu < %zu bytes", *workspace_bytes, need);
+  if (!aligned16(workspace)) return fail(CTR_ERR_UNSUPPORTED, "workspace is not 16-byte aligned");
   if (index_type != CTR_I32 && index_type != CTR_I64)
     return fail(CTR_ERR_INVALID_ARGUMENT, "index_type %d is not CTR_I32 or CTR_I64", index_type);
   if (num_tables < 1) return fail(CTR_ERR_INVALID_ARGUMENT, "num_tables must be >= 1");
@@ -202,7 +214,7 @@ int32_t ctr_embbag_fwd(const void* table, int32_t dtype, int64_t total_rows, int
   return hip_status(ctr::launch_embbag_fwd(table, dtype, total_rows, dim, row_base,
                                            num_tables, indices, index_type == CTR_I64, nnz,
                                            offsets, batch, out, out_stride_b, out_stride_t,
-                                           (hipStream_t)stream),
+                                           workspace, (hipStream_t)stream),
                     "ctr_embbag_fwd");
 }
 

@@ -23,10 +23,13 @@ hipError_t launch_unique(const void* ids, bool ids64, int64_t n, const int64_t* 
                          hipStream_t s);
 
 // embbag.hip (elt: the table's kElt code, ctr_internal.h)
+// The pooling; workspace (embbag_fwd_workspace_bytes) holds the long bags' chunk partials.
+size_t embbag_fwd_workspace_bytes(int64_t nnz, int dim);
 hipError_t launch_embbag_fwd(const void* table, int elt, int64_t total_rows, int dim,
                              const int64_t* row_base, int32_t num_tables, const void* idx,
                              bool idx64, int64_t nnz, const int64_t* offsets, int64_t batch,
-                             float* out, int64_t sb, int64_t st, hipStream_t s);
+                             float* out, int64_t sb, int64_t st, void* workspace,
+                             hipStream_t s);
 hipError_t launch_gather_rows(const void* table, int elt, int64_t total_rows, int dim,
                               const int64_t* rows, const int32_t* num_rows, int64_t capacity,
                               float* out, hipStream_t s);

@@ -37,6 +37,16 @@ __device__ __forceinline__ void accumulate(float* acc, const uint4& x) {
 
 constexpr int kMaxBagsPerGroup = 16;
 
+// A bag of more than kLongBag occurrences is not pooled by the kernels below (they skip its
+// rows and raise a flag in the workspace) but by the long-bag kernels further down: in fixed
+// chunks of kLongChunk occurrences spread over the grid, whose partial sums a fixed pairwise
+// tree then adds.  A long bag is longer than a chunk, so one chunk meets at most two long
+// bags and at most one starts in it.  Without the flag the long-bag kernels return at once.
+constexpr int64_t kLongBag = 4096;
+constexpr int64_t kLongChunk = 4096;
+constexpr int64_t kLongGrid = 1024;             // blocks of the long-bag kernels (grid-stride)
+static_assert(kLongBag >= kLongChunk, "a long bag spans more than one chunk");
+
 // A group of G lanes pools `nbg` consecutive bags: their offsets and table bases go to LDS,
 // their occurrences are walked in order in chunks of kU (indices loaded cooperatively and
 // broadcast by shuffles, kU row loads in flight), and a bag's sum is stored when the walk
@@ -46,7 +56,7 @@ __global__ __launch_bounds__(kThreads) void embbag_fwd_kernel(
     const char* __restrict__ table, int64_t total_rows, int64_t row_bytes, int vecs,
     const int64_t* __restrict__ row_base, const TIdx* __restrict__ idx, int64_t nnz,
     const int64_t* __restrict__ offsets, int64_t batch, int64_t num_bags, int nbg,
-    float* __restrict__ out, int64_t sb, int64_t st) {
+    float* __restrict__ out, int64_t sb, int64_t st, int32_t* __restrict__ long_flag) {
   constexpr int E = TY != kEltF32 ? 8 : 4;
   constexpr int kGroups = kThreads / G;
   constexpr int kU = (VPL == 1 && G <= 8) ? 16 : 8;   // rows in flight per group
@@ -71,14 +81,20 @@ __global__ __launch_bounds__(kThreads) void embbag_fwd_kernel(
 #pragma unroll
     for (int e = 0; e < E; ++e) acc[a][e] = 0.f;
   int cur = 0;
-  auto flush = [&](int j) {
+  auto is_long = [&](int j) { return (int64_t)s_off[grp][j + 1] - s_off[grp][j] > kLongBag; };
+  bool any_long = false;                       // only a range above kLongBag can hold one
+  if (long_flag && o_end - o_beg > kLongBag)
+    for (int j = 0; j < nb; ++j) any_long |= is_long(j);
+  if (any_long && lane == 0) *long_flag = 1;
+  auto flush = [&](int j) {                    // a long bag is written by its own kernels
     const int64_t s = s0 + j;
     const int64_t t = s / batch, b = s - t * batch;
     float* o = out + b * sb + t * st;
+    const bool keep = !(any_long && is_long(j));
 #pragma unroll
     for (int a = 0; a < VPL; ++a) {
       const int vi = a * G + lane;
-      if (vi < vecs) {
+      if (keep && vi < vecs) {
         float4* p = reinterpret_cast<float4*>(o + (int64_t)vi * E);
         p[0] = make_float4(acc[a][0], acc[a][1], acc[a][2], acc[a][3]);
         if (E == 8) p[1] = make_float4(acc[a][4 % E], acc[a][5 % E], acc[a][6 % E], acc[a][7 % E]);
@@ -89,6 +105,16 @@ __global__ __launch_bounds__(kThreads) void embbag_fwd_kernel(
   };
 
   for (int64_t k0 = o_beg; k0 < o_end; k0 += kU) {
+    if (any_long) {
+      // the rows of a long bag are skipped: jump to its end
+      int c = cur;
+      while (c < nb - 1 && k0 >= s_off[grp][c + 1]) ++c;
+      if (is_long(c)) {
+        while (cur <= c) flush(cur++);
+        k0 = (int64_t)s_off[grp][c + 1] - kU;  // the loop's step lands on the bag's end
+        continue;
+      }
+    }
     TIdx iv[kRegs];
 #pragma unroll
     for (int r = 0; r < kRegs; ++r) {
@@ -146,12 +172,19 @@ constexpr double kPoolRows = 128.0;
 constexpr int64_t kPoolMinBlocks = 2048;
 constexpr double kPoolMinRows = 20.0;
 
-template <typename TIdx, int TY, int G, int VPL>
-__global__ __launch_bounds__(kThreads) void embbag_fwd_balanced_kernel(
-    const char* __restrict__ table, int64_t total_rows, int64_t row_bytes, int vecs,
-    const int64_t* __restrict__ row_base, const TIdx* __restrict__ idx, int64_t nnz,
+// The pooling of block blk (bags blk*nbb ..).  Only a block whose range exceeds kLongBag can
+// hold a long bag; there every wave checks all the block's bags (a vote, no barrier).
+// SKIP = false (embbag_fwd_balanced_kernel): a block that holds a long bag raises the flag and
+// pools nothing, leaving all its bags to long_bag_kernel; the others run the plain loop.
+// SKIP = true (long_bag_kernel): only such a block is pooled, by a loop that skips the long
+// bags' rows (the chunked kernels pool those).  Keeping the skipping loop out of the fast
+// kernel keeps that kernel's code as it was: the checks cost Large's pooling about 3 %.
+template <typename TIdx, int TY, int G, int VPL, bool SKIP>
+__device__ __forceinline__ void pool_block(
+    int64_t blk, const char* __restrict__ table, int64_t total_rows, int64_t row_bytes,
+    int vecs, const int64_t* __restrict__ row_base, const TIdx* __restrict__ idx, int64_t nnz,
     const int64_t* __restrict__ offsets, int64_t batch, int64_t num_bags, int nbb,
-    float* __restrict__ out, int64_t sb, int64_t st) {
+    float* __restrict__ out, int64_t sb, int64_t st, int32_t* __restrict__ long_flag) {
   constexpr int E = TY != kEltF32 ? 8 : 4;
   constexpr int kGroups = kThreads / G;
   constexpr int kU = (VPL == 1 && G <= 8) ? 16 : 8;   // rows in flight per group
@@ -165,7 +198,7 @@ __global__ __launch_bounds__(kThreads) void embbag_fwd_balanced_kernel(
   const int lane = threadIdx.x & (G - 1);
   const int grp = threadIdx.x / G;
   const int lane0 = (threadIdx.x & 63) & ~(G - 1);
-  const int64_t s0 = (int64_t)blockIdx.x * nbb;
+  const int64_t s0 = blk * nbb;
   const int nb = (int)clamp64(num_bags - s0, 0, nbb);
   for (int j = threadIdx.x; j <= nb; j += kThreads) s_off[j] = (int32_t)clamp64(offsets[s0 + j], 0, nnz);
   for (int j = threadIdx.x; j < nb; j += kThreads) s_base[j] = row_base ? row_base[(s0 + j) / batch] : 0;
@@ -201,6 +234,22 @@ __global__ __launch_bounds__(kThreads) void embbag_fwd_balanced_kernel(
   const int64_t q0 = o_beg + (int64_t)grp * share;
   const int64_t q1 = q0 + share < o_beg + range ? q0 + share : o_beg + range;
   int32_t fbag = -1, fcont = 0, lbag = -1;
+  auto is_long = [&](int c) { return (int64_t)s_off[c + 1] - s_off[c] > kLongBag; };
+  bool any_long = false;
+  if (long_flag && range > kLongBag) {
+    bool mine = false;
+    for (int j = threadIdx.x & 63; j < nb; j += 64) mine |= is_long(j);
+    any_long = __any(mine);
+  }
+  if constexpr (!SKIP) {
+    if (any_long) {                            // the same in every wave
+      if (threadIdx.x == 0) *long_flag = 1;
+      return;
+    }
+  } else {
+    if (!any_long) return;
+  }
+  constexpr bool kHasLong = SKIP;
   if (q0 < q1) {
     // bag of the share's first occurrence: last c with s_off[c] <= q0 (binary search)
     int c = 0, hi = nb - 1;
@@ -215,7 +264,8 @@ __global__ __launch_bounds__(kThreads) void embbag_fwd_balanced_kernel(
 #pragma unroll
       for (int e = 0; e < E; ++e) acc[a][e] = 0.f;
     auto close_piece = [&](bool bag_ends_here) {
-      if (piece_at_start && bag_ends_here) {
+      if (kHasLong && is_long(c)) {            // pooled by the long-bag kernels
+      } else if (piece_at_start && bag_ends_here) {
         store(out_row(c), acc);
       } else if (!piece_at_start) {            // began before this share
         fbag = c;
@@ -231,6 +281,19 @@ __global__ __launch_bounds__(kThreads) void embbag_fwd_balanced_kernel(
         for (int e = 0; e < E; ++e) acc[a][e] = 0.f;
     };
     for (int64_t k0 = q0; k0 < q1; k0 += kU) {
+      if (kHasLong && is_long(c)) {
+        // the rows of a long bag are skipped: close its (empty) piece, jump to its end
+        close_piece(false);
+        const int64_t e = (int64_t)s_off[c + 1];
+        if (e >= q1) {
+          k0 = q1;
+          break;
+        }
+        while (c < nb - 1 && e >= s_off[c + 1]) ++c;
+        piece_at_start = true;                 // e is where bag c begins
+        k0 = e - kU;                           // the loop's step lands on e
+        continue;
+      }
       TIdx iv[kRegs];
 #pragma unroll
       for (int r = 0; r < kRegs; ++r) {
@@ -307,6 +370,201 @@ __global__ __launch_bounds__(kThreads) void embbag_fwd_balanced_kernel(
     }
   }
 }
+
+template <typename TIdx, int TY, int G, int VPL>
+__global__ __launch_bounds__(kThreads) void embbag_fwd_balanced_kernel(
+    const char* __restrict__ table, int64_t total_rows, int64_t row_bytes, int vecs,
+    const int64_t* __restrict__ row_base, const TIdx* __restrict__ idx, int64_t nnz,
+    const int64_t* __restrict__ offsets, int64_t batch, int64_t num_bags, int nbb,
+    float* __restrict__ out, int64_t sb, int64_t st, int32_t* __restrict__ long_flag) {
+  pool_block<TIdx, TY, G, VPL, false>(blockIdx.x, table, total_rows, row_bytes, vecs, row_base,
+                                      idx, nnz, offsets, batch, num_bags, nbb, out, sb, st,
+                                      long_flag);
+}
+
+// ----------------------------------------------------------------------------- long bags
+// The last bag j with offsets[j] <= p, j < num_bags (binary search; with non-decreasing
+// offsets, offsets[0] <= p < offsets[num_bags], it is the bag that holds occurrence p).
+__device__ __forceinline__ int64_t bag_at(const int64_t* __restrict__ offsets,
+                                          int64_t num_bags, int64_t p) {
+  int64_t lo = 0, hi = num_bags;
+  while (hi - lo > 1) {
+    const int64_t mid = (lo + hi) >> 1;
+    if (offsets[mid] <= p) lo = mid; else hi = mid;
+  }
+  return lo;
+}
+
+// long_bag_kernel, first (balanced pooling only, nbb > 0): the blocks of the balanced kernel
+// that hold a long bag, pooled by pool_block<SKIP = true>.  Then the chunks: chunk
+// k = occurrences [k C, (k + 1) C), C = kLongChunk, one block each.  For each long bag
+// the chunk meets (at most two), the block sums the bag's rows inside the chunk: the piece is
+// split evenly over the lane groups, each adding its share in occurrence order with kU loads
+// in flight, and the groups' sums are joined by a pairwise tree in LDS.  The sum goes to
+// partial slot 2k (the bag holding the chunk's first occurrence) or 2k + 1 (a long bag that
+// starts later in the chunk); starts[k] is the long bag that starts in chunk k, or -1.
+template <typename TIdx, int TY, int G, int VPL>
+__global__ __launch_bounds__(kThreads) void long_bag_kernel(
+    const char* __restrict__ table, int64_t total_rows, int64_t row_bytes, int vecs,
+    const int64_t* __restrict__ row_base, const TIdx* __restrict__ idx, int64_t nnz,
+    const int64_t* __restrict__ offsets, int64_t batch, int64_t num_bags, int nbb,
+    float* __restrict__ out, int64_t sb, int64_t st, int32_t* __restrict__ long_flag,
+    int64_t* __restrict__ starts, float* __restrict__ partials) {
+  constexpr int E = TY != kEltF32 ? 8 : 4;
+  constexpr int kGroups = kThreads / G;
+  constexpr int kU = (VPL == 1 && G <= 8) ? 16 : 8;
+  constexpr int kRegs = (kU + G - 1) / G;
+  constexpr int kW = G * VPL * E;
+  __shared__ float s_sum[kGroups][kW];
+  __shared__ int64_t s_long[2];
+  const int64_t chunks = (nnz + kLongChunk - 1) / kLongChunk;
+  if (*long_flag == 0) {                       // no long bag in this call
+    for (int64_t k = (int64_t)blockIdx.x * kThreads + threadIdx.x; k < chunks;
+         k += (int64_t)gridDim.x * kThreads)
+      starts[k] = -1;
+    return;
+  }
+  if constexpr (VPL == 1) {
+    if (nbb > 0) {
+      const int64_t nblocks = (num_bags + nbb - 1) / nbb;
+      for (int64_t blk = blockIdx.x; blk < nblocks; blk += gridDim.x) {
+        __syncthreads();                       // the previous block is done with the LDS
+        pool_block<TIdx, TY, G, VPL, true>(blk, table, total_rows, row_bytes, vecs, row_base,
+                                           idx, nnz, offsets, batch, num_bags, nbb, out, sb,
+                                           st, long_flag);
+      }
+    }
+  }
+  const int lane = threadIdx.x & (G - 1);
+  const int grp = threadIdx.x / G;
+  const int lane0 = (threadIdx.x & 63) & ~(G - 1);
+  for (int64_t k = blockIdx.x; k < chunks; k += gridDim.x) {
+  const int64_t c0 = k * kLongChunk;
+  const int64_t c1 = c0 + kLongChunk < nnz ? c0 + kLongChunk : nnz;
+  const int dim = vecs * E;
+  auto off = [&](int64_t j) { return clamp64(offsets[j], 0, nnz); };
+  __syncthreads();                             // the previous chunk is done with s_long
+  if (threadIdx.x == 0) s_long[0] = s_long[1] = -1;
+  __syncthreads();
+  // the bags meeting the chunk, from the one holding c0 to the one holding c1 - 1
+  const int64_t jf = bag_at(offsets, num_bags, c0);
+  const int64_t jl = bag_at(offsets, num_bags, c1 - 1);
+  for (int64_t j = jf + threadIdx.x; j <= jl; j += kThreads) {
+    const int64_t b0 = off(j), b1 = off(j + 1);
+    if (b1 - b0 > kLongBag) s_long[j == jf ? 0 : 1] = j;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const int64_t a = s_long[0];
+    starts[k] = (a >= 0 && off(a) == c0) ? a : s_long[1];
+  }
+  for (int w = 0; w < 2; ++w) {
+    const int64_t j = s_long[w];
+    if (j < 0) continue;                       // the same for the whole block
+    const int64_t b0 = off(j), b1 = off(j + 1);
+    const int64_t p0 = b0 > c0 ? b0 : c0, p1 = b1 < c1 ? b1 : c1;
+    const int64_t share = (p1 - p0 + kGroups - 1) / kGroups;
+    const int64_t q0 = p0 + grp * share < p1 ? p0 + grp * share : p1;
+    const int64_t q1 = q0 + share < p1 ? q0 + share : p1;
+    const int64_t base = row_base ? row_base[j / batch] : 0;
+    float acc[VPL][E];
+#pragma unroll
+    for (int a = 0; a < VPL; ++a)
+#pragma unroll
+      for (int e = 0; e < E; ++e) acc[a][e] = 0.f;
+    for (int64_t k0 = q0; k0 < q1; k0 += kU) {
+      TIdx iv[kRegs];
+#pragma unroll
+      for (int r = 0; r < kRegs; ++r) {
+        const int e = r * G + lane;
+        const int64_t kk = k0 + e;
+        iv[r] = (e < kU && kk < q1) ? idx[kk] : (TIdx)0;
+      }
+      uint4 rv[kU][VPL];
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        const int64_t key = base + (int64_t)__shfl(iv[u / G], lane0 + (u % G), 64);
+        const bool live = k0 + u < q1;
+        const bool ok = key >= 0 && key < total_rows;
+#pragma unroll
+        for (int a = 0; a < VPL; ++a) {
+          const int vi = a * G + lane;
+          if (live && ok && vi < vecs)
+            rv[u][a] = *reinterpret_cast<const uint4*>(table + key * row_bytes + (int64_t)vi * 16);
+          else if (live && !ok)
+            rv[u][a] = make_uint4(0x7FC00000u, 0x7FC00000u, 0x7FC00000u, 0x7FC00000u);  // NaN
+          else
+            rv[u][a] = make_uint4(0u, 0u, 0u, 0u);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        if (k0 + u >= q1) break;
+#pragma unroll
+        for (int a = 0; a < VPL; ++a) accumulate<TY>(acc[a], rv[u][a]);
+      }
+    }
+#pragma unroll
+    for (int a = 0; a < VPL; ++a)
+#pragma unroll
+      for (int e = 0; e < E; ++e) s_sum[grp][(a * G + lane) * E + e] = acc[a][e];
+    __syncthreads();
+    for (int h = kGroups / 2; h > 0; h >>= 1) {  // pairwise over the groups
+      if (grp < h) {
+#pragma unroll
+        for (int a = 0; a < VPL; ++a)
+#pragma unroll
+          for (int e = 0; e < E; ++e)
+            s_sum[grp][(a * G + lane) * E + e] += s_sum[grp + h][(a * G + lane) * E + e];
+      }
+      __syncthreads();
+    }
+    float* dst = partials + (2 * k + w) * (int64_t)dim;
+    for (int c = threadIdx.x; c < dim; c += kThreads) dst[c] = s_sum[0][c];
+    __syncthreads();                           // s_sum is reused by the next bag
+  }
+  }
+}
+
+// Long bag starts[k] (chunk k holds its first occurrence) spans chunks k .. k2: its m pieces
+// sit in slots 2k + (0 if it starts at the chunk's first occurrence, else 1), 2(k + 1), ...,
+// 2 k2.  One block adds them pairwise in place (level h adds piece t + h into piece t for t a
+// multiple of 2h), a fixed tree of depth ceil(log2 m), and writes the bag's output row.
+// The flag is lowered here for the next call: the partials kernel, its only reader, is done.
+__global__ __launch_bounds__(kThreads) void long_bag_combine_kernel(
+    const int64_t* __restrict__ offsets, int64_t nnz, int64_t batch, int64_t num_bags,
+    int32_t* __restrict__ long_flag, const int64_t* __restrict__ starts,
+    float* __restrict__ partials, int dim, float* __restrict__ out, int64_t sb, int64_t st) {
+  if (blockIdx.x == 0 && threadIdx.x == 0) *long_flag = 0;
+  const int64_t chunks = (nnz + kLongChunk - 1) / kLongChunk;
+  for (int64_t k = blockIdx.x; k < chunks; k += gridDim.x) {
+  const int64_t j = starts[k];
+  if (j < 0 || j >= num_bags) continue;        // the same for the whole block
+  const int64_t c0 = k * kLongChunk;
+  const int64_t b0 = clamp64(offsets[j], 0, nnz), b1 = clamp64(offsets[j + 1], 0, nnz);
+  if (b1 <= b0 || b0 < c0) continue;           // (only with offsets out of order)
+  const int64_t k2 = (b1 - 1) / kLongChunk;
+  const int64_t m = k2 - k + 1;
+  auto slot = [&](int64_t t) -> float* {
+    return partials + (t == 0 ? 2 * k + (b0 > c0 ? 1 : 0) : 2 * (k + t)) * (int64_t)dim;
+  };
+  for (int64_t h = 1; h < m; h <<= 1) {
+    const int64_t pairs = (m - 1 - h) / (2 * h) + 1;         // t = 0, 2h, ... with t + h < m
+    for (int64_t q = threadIdx.x; q < pairs * dim; q += kThreads) {
+      const int64_t t = (q / dim) * 2 * h;
+      const int c = (int)(q - (q / dim) * dim);
+      slot(t)[c] += slot(t + h)[c];
+    }
+    __syncthreads();
+  }
+  const int64_t t = j / batch, b = j - t * batch;
+  float* o = out + b * sb + t * st;
+  const float* r = slot(0);
+  for (int c = threadIdx.x; c < dim; c += kThreads) o[c] = r[c];
+  __syncthreads();                             // before the next bag's tree
+  }
+}
+
 
 // E[u] = W[rows[u]] widened to fp32, u < min(num_rows, capacity).
 template <int TY, int G, int VPL>
@@ -485,10 +743,18 @@ __global__ __launch_bounds__(kThreads) void validate_csr_kernel(
     else { constexpr int TY = kEltF32; __VA_ARGS__; }                       \
   } while (0)
 
+// Workspace: the flag (256 bytes), starts[chunks] (int64, to a 256-byte multiple), then the
+// partial rows [2 chunks][dim] (fp32).
+size_t embbag_fwd_workspace_bytes(int64_t nnz, int dim) {
+  const int64_t chunks = nnz > kLongBag ? (nnz + kLongChunk - 1) / kLongChunk : 0;
+  return 256 + ((size_t)chunks * 8 + 255) / 256 * 256 + (size_t)chunks * 2 * (size_t)dim * 4;
+}
+
 hipError_t launch_embbag_fwd(const void* table, int elt, int64_t total_rows, int dim,
                              const int64_t* row_base, int32_t num_tables, const void* idx,
                              bool idx64, int64_t nnz, const int64_t* offsets, int64_t batch,
-                             float* out, int64_t sb, int64_t st, hipStream_t s) {
+                             float* out, int64_t sb, int64_t st, void* workspace,
+                             hipStream_t s) {
   const int E = elt != kEltF32 ? 8 : 4;
   const int vecs = dim / E;
   const RowGeom rg = row_geom(vecs);
@@ -497,19 +763,22 @@ hipError_t launch_embbag_fwd(const void* table, int elt, int64_t total_rows, int
   if (num_bags == 0) return hipSuccess;
   const char* tb = static_cast<const char*>(table);
   const double avg = (double)nnz / (double)num_bags;
+  // the long-bag flag: only needed when a bag can be long
+  int32_t* long_flag = nnz > kLongBag ? static_cast<int32_t*>(workspace) : nullptr;
 #define CTR_FWD_LAUNCH(KERNEL, BLOCKS, PER)                                                    \
   do {                                                                                        \
     CTR_DISPATCH_ELT(elt, {                                                                   \
       if (idx64)                                                                              \
         KERNEL<int64_t, TY, G, VPL><<<(unsigned)(BLOCKS), kThreads, 0, s>>>(                  \
             tb, total_rows, row_bytes, vecs, row_base, (const int64_t*)idx, nnz, offsets,     \
-            batch, num_bags, PER, out, sb, st);                                               \
+            batch, num_bags, PER, out, sb, st, long_flag);                                    \
       else                                                                                    \
         KERNEL<int32_t, TY, G, VPL><<<(unsigned)(BLOCKS), kThreads, 0, s>>>(                  \
             tb, total_rows, row_bytes, vecs, row_base, (const int32_t*)idx, nnz, offsets,     \
-            batch, num_bags, PER, out, sb, st);                                               \
+            batch, num_bags, PER, out, sb, st, long_flag);                                    \
     });                                                                                       \
   } while (0)
+  int nbb_used = 0;                               // bags per block of the balanced kernel
   CTR_DISPATCH_G_VPL(rg.G, rg.VPL, {
     constexpr int kGroups = kThreads / G;
     if (VPL == 1) {
@@ -521,6 +790,7 @@ hipError_t launch_embbag_fwd(const void* table, int elt, int64_t total_rows, int
       if (nbb > kMaxBagsPerBlock) nbb = kMaxBagsPerBlock;
       if (nbb < 1) nbb = 1;
       const int64_t blocks = (num_bags + nbb - 1) / nbb;
+      nbb_used = (int)nbb;
       CTR_FWD_LAUNCH(embbag_fwd_balanced_kernel, blocks, (int)nbb);
       break;
     }
@@ -536,6 +806,27 @@ hipError_t launch_embbag_fwd(const void* table, int elt, int64_t total_rows, int
     CTR_FWD_LAUNCH(embbag_fwd_kernel, blocks, nbg);
   });
 #undef CTR_FWD_LAUNCH
+  if (!long_flag) return hipGetLastError();        // no bag can be long
+  // long bags: chunk partials, then each bag's pairwise sum (which lowers the flag again)
+  const int64_t chunks = (nnz + kLongChunk - 1) / kLongChunk;
+  const unsigned lgrid = (unsigned)(chunks < kLongGrid ? chunks : kLongGrid);
+  int64_t* starts = reinterpret_cast<int64_t*>(static_cast<char*>(workspace) + 256);
+  float* partials = reinterpret_cast<float*>(static_cast<char*>(workspace) + 256 +
+                                             ((size_t)chunks * 8 + 255) / 256 * 256);
+  CTR_DISPATCH_G_VPL(rg.G, rg.VPL, {
+    CTR_DISPATCH_ELT(elt, {
+      if (idx64)
+        long_bag_kernel<int64_t, TY, G, VPL><<<lgrid, kThreads, 0, s>>>(
+            tb, total_rows, row_bytes, vecs, row_base, (const int64_t*)idx, nnz, offsets,
+            batch, num_bags, nbb_used, out, sb, st, long_flag, starts, partials);
+      else
+        long_bag_kernel<int32_t, TY, G, VPL><<<lgrid, kThreads, 0, s>>>(
+            tb, total_rows, row_bytes, vecs, row_base, (const int32_t*)idx, nnz, offsets,
+            batch, num_bags, nbb_used, out, sb, st, long_flag, starts, partials);
+    });
+  });
+  long_bag_combine_kernel<<<lgrid, kThreads, 0, s>>>(offsets, nnz, batch, num_bags, long_flag,
+                                                     starts, partials, dim, out, sb, st);
   return hipGetLastError();
 }
 

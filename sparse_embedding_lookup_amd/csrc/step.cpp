@@ -64,16 +64,18 @@ int32_t forward_part(const ctr_step_t* d, int set, hipStream_t s, void* mark_beg
   if (d->kind == CTR_STEP_POOLED_INTERACTION) {
     const int64_t F = (int64_t)d->num_tables + 1;
     CTR_TRY(mark(mark_begin, s));
+    size_t wsb = d->ws_pool_bytes;
     CTR_TRY(ctr_embbag_fwd(d->table, d->dtype, d->total_rows, d->dim, d->row_base, d->num_tables,
                            d->indices, d->index_type, d->nnz, d->offsets, d->batch,
-                           d->Z + d->dim, F * d->dim, d->dim, s));
+                           d->Z + d->dim, F * d->dim, d->dim, d->ws_pool, &wsb, s));
     return mark(mark_end, s);
   }
   CTR_TRY(ctr_gather_rows(d->table, d->dtype, d->total_rows, d->dim, d->uniq[set],
                           d->num_unique[set], d->nnz, d->E, s));
   CTR_TRY(mark(mark_begin, s));
+  size_t wsb = d->ws_pool_bytes;
   CTR_TRY(ctr_embbag_fwd(d->E, CTR_F32, d->nnz, d->dim, nullptr, 1, d->inverse[set], CTR_I32,
-                         d->nnz, d->offsets, d->nnz, d->out, d->dim, 0, s));
+                         d->nnz, d->offsets, d->nnz, d->out, d->dim, 0, d->ws_pool, &wsb, s));
   return mark(mark_end, s);
 }
 
@@ -135,6 +137,7 @@ int32_t ctr_step_run_deep(const ctr_step_t* d, int64_t k, void* main_stream, voi
   if (d->rounding != CTR_ROUND_NEAREST && d->rounding != CTR_ROUND_STOCHASTIC)
     return invalid("unknown rounding");
   if (d->grad_dtype != CTR_F32 && d->grad_dtype != CTR_BF16) return invalid("unknown grad_dtype");
+  if (!d->ws_pool) return invalid("the pooling workspace ws_pool is required");
   if (d->mark_stage != CTR_MARK_POOLING && d->mark_stage != CTR_MARK_BACKWARD)
     return invalid("unknown mark_stage");
   if (!side_stream0 || !side_stream1 || !events) return invalid("two side streams and six events are required");
@@ -173,6 +176,7 @@ int32_t ctr_step_run(const ctr_step_t* d, int64_t k, int32_t schedule, void* mai
   if (d->rounding != CTR_ROUND_NEAREST && d->rounding != CTR_ROUND_STOCHASTIC)
     return invalid("unknown rounding");
   if (d->grad_dtype != CTR_F32 && d->grad_dtype != CTR_BF16) return invalid("unknown grad_dtype");
+  if (!d->ws_pool) return invalid("the pooling workspace ws_pool is required");
   if (d->mark_stage != CTR_MARK_POOLING && d->mark_stage != CTR_MARK_BACKWARD)
     return invalid("unknown mark_stage");
   if (schedule < CTR_SCHEDULE_SERIAL || schedule > CTR_SCHEDULE_PIPELINED_OVERLAP)

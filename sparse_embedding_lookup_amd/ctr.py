@@ -60,7 +60,8 @@ class CtrStep(ctypes.Structure):
                 ("sorted_src", _P * 3), ("rounding", ctypes.c_int32),
                 ("sr_seed", ctypes.c_uint64), ("grad_dtype", ctypes.c_int32),
                 ("ws_unique2", _P), ("ws_unique2_bytes", ctypes.c_size_t),
-                ("mark_stage", ctypes.c_int32), ("max_table_rows", ctypes.c_int64)]
+                ("mark_stage", ctypes.c_int32), ("max_table_rows", ctypes.c_int64),
+                ("ws_pool", _P), ("ws_pool_bytes", ctypes.c_size_t)]
 
 _lib = None
 
@@ -94,7 +95,8 @@ def load() -> ctypes.CDLL:
         "ctr_unique_ids": (i32, [P, i32, i64, P, i64, i32, P, i64, i64, i64, P, P, P, P, P, P, P,
                                  PS, P]),
         "ctr_gather_rows": (i32, [P, i32, i64, i32, P, P, i64, P, P]),
-        "ctr_embbag_fwd": (i32, [P, i32, i64, i32, P, i32, P, i32, i64, P, i64, P, i64, i64, P]),
+        "ctr_embbag_fwd": (i32, [P, i32, i64, i32, P, i32, P, i32, i64, P, i64, P, i64, i64, P,
+                                 PS, P]),
         "ctr_embbag_bwd": (i32, [P, i64, i64, P, i64, i32, i32, i64, P, P, P, P, P, P, PS, P]),
         "ctr_embbag_bwd_sgd": (i32, [P, i32, i64, i64, P, i64, i32, i64, P, P, P, i32, i64,
                                      i32, P, f32, i32, u64, P, P, PS, P]),
@@ -265,14 +267,30 @@ def ctr_gather_rows(table: torch.Tensor, rows: torch.Tensor, num_rows: torch.Ten
     return _run("ctr_gather_rows", args, stream, prepare, out)
 
 
+def embbag_fwd_workspace_bytes(nnz: int, dim: int) -> int:
+    """Workspace of ctr_embbag_fwd (the library's two-call query)."""
+    wsb = ctypes.c_size_t(0)
+    _check("ctr_embbag_fwd", load().ctr_embbag_fwd(None, CTR_F32, 0, dim, None, 1, None, CTR_I64,
+                                                   nnz, None, 0, None, 0, 0, None,
+                                                   ctypes.byref(wsb), None))
+    return wsb.value
+
+
 def ctr_embbag_fwd(table: torch.Tensor, indices: torch.Tensor, offsets: torch.Tensor,
                    batch: int, num_tables: int, out: torch.Tensor, out_stride_b: int,
                    out_stride_t: int, row_base: Optional[torch.Tensor] = None,
-                   stream=None, prepare: bool = False):
+                   workspace: Optional[torch.Tensor] = None, stream=None,
+                   prepare: bool = False):
+    """Sum pooling of the bags into out; ``workspace`` (uint8, from embbag_fwd_workspace_bytes)
+    holds the partial sums of bags longer than 4096 occurrences (allocated when None)."""
     total_rows, dim = table.shape
+    nnz = indices.numel()
+    if workspace is None:
+        workspace = _workspace(embbag_fwd_workspace_bytes(nnz, dim), table.device)
+    wsb = ctypes.c_size_t(workspace.numel())
     args = (_ptr(table), _dtype_code(table), total_rows, dim, _ptr(row_base), num_tables,
-            _ptr(indices), _index_code(indices), indices.numel(), _ptr(offsets), batch, _ptr(out),
-            out_stride_b, out_stride_t)
+            _ptr(indices), _index_code(indices), nnz, _ptr(offsets), batch, _ptr(out),
+            out_stride_b, out_stride_t, _ptr(workspace), ctypes.byref(wsb))
     return _run("ctr_embbag_fwd", args, stream, prepare, out)
 
 

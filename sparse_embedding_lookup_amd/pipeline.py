@@ -103,6 +103,8 @@ class FrontEnd:
                                      device=dv)
         self.ws_bwd = torch.empty(max(ctr.embbag_bwd_workspace_bytes(n, d), 256),
                                   dtype=torch.uint8, device=dv)
+        self.ws_pool = torch.zeros(max(ctr.embbag_fwd_workspace_bytes(max(n, 1), d), 256),
+                                   dtype=torch.uint8, device=dv)
         self._sets = [self._unique_buffers(n, dv) for _ in range(3 if pipelined else 1)]
         self._calls = []
         self.side = None
@@ -145,7 +147,7 @@ class FrontEnd:
                 workspace=self.ws_unique, out=self._unique_out, sorted_src=self.sorted_src, **P)
             self._c_embbag_fwd = ctr.ctr_embbag_fwd(
                 self.table, self.indices, self.offsets, w.batch, w.num_tables, self.Z[:, 1:, :],
-                F * d, d, row_base=self.row_base, **P)
+                F * d, d, row_base=self.row_base, workspace=self.ws_pool, **P)
             self._c_interaction_fwd = ctr.ctr_dot_interaction_fwd(self.Z, self.compute, self.R, **P)
             self._c_embbag_interaction_fwd = ctr.ctr_embbag_interaction_fwd(
                 self.table, self.indices, self.offsets, self.Z, self.compute, self.R,
@@ -164,7 +166,8 @@ class FrontEnd:
             self._c_gather_rows = ctr.ctr_gather_rows(self.table, self.uniq, self.num_unique,
                                                       self.nnz, out=self.E, **P)
             self._c_embbag_fwd = ctr.ctr_embbag_fwd(self.E, self.inverse, self.offsets, self.nnz,
-                                                    1, self.out, d, 0, **P)
+                                                    1, self.out, d, 0, workspace=self.ws_pool,
+                                                    **P)
             if not self.fused:
                 self._c_embbag_bwd = ctr.ctr_embbag_bwd(
                     self.dout, d, 0, self.offsets, self.nnz, 1, d, None, None,
@@ -432,6 +435,7 @@ class FrontEnd:
             self.ws_unique2 = torch.empty_like(self.ws_unique)
             d.ws_unique2, d.ws_unique2_bytes = P(self.ws_unique2), self.ws_unique2.numel()
         d.ws_bwd, d.ws_bwd_bytes = P(self.ws_bwd), self.ws_bwd.numel()
+        d.ws_pool, d.ws_pool_bytes = P(self.ws_pool), self.ws_pool.numel()
         for i in range(3):
             b = self._sets[min(i, len(self._sets) - 1)]
             d.uniq[i], d.inverse[i] = P(b["uniq"]), P(b["inverse"])

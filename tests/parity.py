@@ -74,12 +74,37 @@ def segreduce_depth(n, dim, bf16_grads):
     return levels * ((kps - 1) + (slots - 1))
 
 
-def pool_eps(offsets, batch, num_tables):
-    """Per-bag bound g_{L-1} of the pooled sums, shaped [batch, num_tables, 1]: the kernels
+LONG_BAG = 4096          # a longer bag is pooled in chunks of LONG_CHUNK occurrences
+LONG_CHUNK = 4096
+
+
+def long_bag_depth(L, dim, table):
+    """Most roundings on a path of the pooled sum of a bag of L > LONG_BAG occurrences: a
+    chunk's piece is split over the block's lane groups (256 / G of them, G = 16-byte vectors
+    per row rounded up to a power of two, at most 64), each adding at most
+    ceil(LONG_CHUNK / groups) rows in order, the groups joined pairwise (log2 groups), and the
+    bag's chunk sums (at most ceil(L / LONG_CHUNK) + 1 pieces) added by a pairwise tree."""
+    per = 4 if table == "f32" else 8
+    vecs = max(1, int(dim) // per)
+    G = 1
+    while G < 64 and G < vecs:
+        G *= 2
+    groups = 256 // G
+    share = -(-LONG_CHUNK // groups)
+    pieces = -(-int(L) // LONG_CHUNK) + 1
+    return (share - 1) + int(np.log2(groups)) + int(np.ceil(np.log2(pieces)))
+
+
+def pool_eps(offsets, batch, num_tables, dim=None, table="f32"):
+    """Per-bag bound of the pooled sums, shaped [batch, num_tables, 1]: g_{L-1} (the kernels
     add a bag's rows one after another within a share and join the shares' pieces in order,
-    so no path has more than L - 1 roundings."""
+    so no path has more than L - 1 roundings); with dim given, a bag longer than LONG_BAG
+    gets g_D with D = long_bag_depth (its chunked tree)."""
     lens = np.diff(np.asarray(offsets, np.int64)).reshape(num_tables, batch).T
     k = np.maximum(lens - 1, 0).astype(np.float64)
+    if dim is not None:
+        for idx in zip(*np.nonzero(lens > LONG_BAG)):
+            k[idx] = min(k[idx], long_bag_depth(lens[idx], dim, table))
     return (k * U32 / (1.0 - k * U32))[:, :, None]
 
 

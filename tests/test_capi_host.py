@@ -89,13 +89,26 @@ def test_unique_workspace_query_and_bad_args():
 def test_embbag_fwd_bad_args():
     lib = _lib()
     ok = dict(table=FAKE, dtype=0, rows=100, dim=16, rb=None, T=1, idx=FAKE, it=1, nnz=10,
-              off=FAKE, B=10, out=FAKE, sb=16, st=0)
+              off=FAKE, B=10, out=FAKE, sb=16, st=0, ws=FAKE, wsb=1 << 20)
 
     def call(**kw):
         a = dict(ok, **kw)
+        wsb = ctypes.c_size_t(a["wsb"])
         return lib.ctr_embbag_fwd(a["table"], a["dtype"], a["rows"], a["dim"], a["rb"], a["T"],
                                   a["idx"], a["it"], a["nnz"], a["off"], a["B"], a["out"],
-                                  a["sb"], a["st"], None)
+                                  a["sb"], a["st"], a["ws"], ctypes.byref(wsb), None)
+
+    # the workspace query needs nnz and dim only: 256 bytes up to 4096 occurrences, then the
+    # long bags' chunk partials
+    q = ctypes.c_size_t(0)
+    assert lib.ctr_embbag_fwd(None, 0, 0, 16, None, 1, None, 1, 4096, None, 0, None, 0, 0, None,
+                              ctypes.byref(q), None) == ctr.CTR_OK and q.value == 256
+    assert lib.ctr_embbag_fwd(None, 0, 0, 16, None, 1, None, 1, 1 << 20, None, 0, None, 0, 0,
+                              None, ctypes.byref(q), None) == ctr.CTR_OK
+    assert q.value == 256 + 256 * 8 + 256 * 2 * 16 * 4
+    assert ctr.embbag_fwd_workspace_bytes(1 << 20, 16) == q.value
+    assert call(wsb=q.value - 1, nnz=1 << 20) == ctr.CTR_ERR_WORKSPACE_TOO_SMALL
+    assert call(ws=MISALIGNED) == ctr.CTR_ERR_UNSUPPORTED
 
     assert call(table=None) == ctr.CTR_ERR_INVALID_ARGUMENT
     assert call(dtype=5) == ctr.CTR_ERR_INVALID_ARGUMENT

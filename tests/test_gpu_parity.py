@@ -278,7 +278,8 @@ def test_embbag_fwd_matches_oracle(name, itype):
     ctr.ctr_embbag_fwd(t, gi, dev(off), B, T, out, T * dim, dim, row_base=dev(rb))
     got = host(out)
     want, mag = orc.embbag_fwd(tab, ids, off, B)
-    assert_within(got, want, pool_eps(off, B, T) * mag, "embbag_fwd " + name, mag=mag)
+    assert_within(got, want, pool_eps(off, B, T, dim, dtype) * mag, "embbag_fwd " + name,
+                  mag=mag)
     # bags of one occurrence are exact row copies, empty bags exact zeros
     lens = np.diff(off).reshape(T, B).T
     single = lens <= 1
