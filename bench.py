@@ -96,7 +96,9 @@ def stage_bytes(w, U):
             "embbag_fwd": n * rb + 8 * n + 8 * (nb + 1) + 4 * nb * d,
             "interaction_fwd": 4 * B * F * d + 4 * B * (d + P),
             "interaction_bwd": 4 * B * (d + P) + 8 * B * F * d,
-            "unique": 8 * n + 8 * (nb + 1) + 4 * n + 4 * n + 12 * U + 4 * U,
+            # the pooled step's unique: ids and offsets in; the distinct rows and sorted_src
+            # (16 bytes per position, the backward's input) out
+            "unique": 8 * n + 8 * (nb + 1) + 16 * n + 8 * U,
             "embbag_bwd": sg * n * d + 8 * n + 4 * U * d,
             "sparse_sgd": 2 * U * rb + 4 * U * d + 8 * U,
             "embbag_bwd_sgd": sg * n * d + 8 * n + 2 * U * rb,
@@ -692,7 +694,10 @@ def main():
     if args.rounding == "stochastic" and w.dtype != "bf16":
         print("--rounding stochastic needs a bf16-table workload (criteo, large)", file=sys.stderr)
         sys.exit(2)
-    fe = FrontEnd(w, "cuda", pipelined=pipelined, rounding=args.rounding)
+    # the pooled step's unique fills what its backward reads (no inverse map: nothing in the
+    # pooled step reads it); the batch-matrix step pools through the inverse map
+    fe = FrontEnd(w, "cuda", pipelined=pipelined, rounding=args.rounding,
+                  lean_unique=w.interaction)
     st = fe.stages()
     torch.cuda.synchronize()
     if args.copy_calibration:

@@ -88,6 +88,9 @@ const char* ctr_last_error_message(void);
  * Outputs (a2), with U = number of distinct keys:
  *   uniq[u]          distinct keys ascending (signed compare), u < U          int64 [n]
  *   inverse[i]       u such that uniq[u] == key(i)                            int32 [n]
+ *                    (nullable: a caller that reads sorted_src instead, as the backward of
+ *                    the pooling does, can leave the map out; with bags, 32-bit keys and no
+ *                    perm either, the sort then moves keys and bags only)
  *   num_unique[0]    U                                                        int32 (device)
  *   perm[p]          occurrence at sorted position p, ties in occurrence order int32 [n]
  *                    (nullable)
@@ -481,7 +484,9 @@ typedef struct {
   void* ws_bwd;
   size_t ws_bwd_bytes;
   int64_t* uniq[CTR_STEP_SETS];
-  int32_t* inverse[CTR_STEP_SETS];
+  int32_t* inverse[CTR_STEP_SETS];            /* the batch-matrix step pools through it; the
+                                                 pooled step may leave it NULL (nothing in it
+                                                 reads the map) */
   int32_t* num_unique[CTR_STEP_SETS];
   int32_t* perm[CTR_STEP_SETS];               /* nullable */
   int32_t* seg_offsets[CTR_STEP_SETS];        /* nullable */

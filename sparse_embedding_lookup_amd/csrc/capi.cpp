@@ -130,8 +130,8 @@ int32_t ctr_unique_ids(const void* ids, int32_t id_type, int64_t n, const int64_
     return fail(CTR_ERR_WORKSPACE_TOO_SMALL, "workspace %zu < %zu bytes", *workspace_bytes, need);
   if (!aligned16(workspace)) return fail(CTR_ERR_UNSUPPORTED, "workspace is not 16-byte aligned");
   if (!num_unique) return fail(CTR_ERR_INVALID_ARGUMENT, "num_unique is NULL");
-  if (n > 0 && (!ids || !uniq || !inverse))
-    return fail(CTR_ERR_INVALID_ARGUMENT, "ids, uniq and inverse are required");
+  if (n > 0 && (!ids || !uniq))
+    return fail(CTR_ERR_INVALID_ARGUMENT, "ids and uniq are required");
   if (sorted_src && (reinterpret_cast<uintptr_t>(sorted_src) & 15u))
     return fail(CTR_ERR_UNSUPPORTED, "sorted_src is not 16-byte aligned");
   int bits;

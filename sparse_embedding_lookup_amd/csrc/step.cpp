@@ -138,6 +138,9 @@ int32_t ctr_step_run_deep(const ctr_step_t* d, int64_t k, void* main_stream, voi
     return invalid("unknown rounding");
   if (d->grad_dtype != CTR_F32 && d->grad_dtype != CTR_BF16) return invalid("unknown grad_dtype");
   if (!d->ws_pool) return invalid("the pooling workspace ws_pool is required");
+  if (d->kind == CTR_STEP_BATCH_MATRIX)
+    for (int j = 0; j < CTR_STEP_SETS; ++j)
+      if (!d->inverse[j]) return invalid("the batch-matrix step pools through inverse[]");
   if (d->mark_stage != CTR_MARK_POOLING && d->mark_stage != CTR_MARK_BACKWARD)
     return invalid("unknown mark_stage");
   if (!side_stream0 || !side_stream1 || !events) return invalid("two side streams and six events are required");
@@ -177,6 +180,9 @@ int32_t ctr_step_run(const ctr_step_t* d, int64_t k, int32_t schedule, void* mai
     return invalid("unknown rounding");
   if (d->grad_dtype != CTR_F32 && d->grad_dtype != CTR_BF16) return invalid("unknown grad_dtype");
   if (!d->ws_pool) return invalid("the pooling workspace ws_pool is required");
+  if (d->kind == CTR_STEP_BATCH_MATRIX)
+    for (int j = 0; j < CTR_STEP_SETS; ++j)
+      if (!d->inverse[j]) return invalid("the batch-matrix step pools through inverse[]");
   if (d->mark_stage != CTR_MARK_POOLING && d->mark_stage != CTR_MARK_BACKWARD)
     return invalid("unknown mark_stage");
   if (schedule < CTR_SCHEDULE_SERIAL || schedule > CTR_SCHEDULE_PIPELINED_OVERLAP)

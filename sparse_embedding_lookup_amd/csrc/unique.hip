@@ -301,14 +301,16 @@ struct DownsweepSmem {
   uint32_t tmp[4];
 };
 
-// IDENT: payload of pass 0 is the element index.  FUSED: few blocks, so this block sums the
+// IDENT: payload of pass 0 is the element index.  VAL: the occurrence payload is carried at
+// all (not when the caller wants neither the inverse map nor the permutation and the bags
+// ride along: then keys and bags alone move).  FUSED: few blocks, so this block sums the
 // digit counts of the blocks before it itself instead of reading a separate scan's output.
 // B16: a second payload, the occurrence's 16-bit sample index, rides along (pass 0 reads it
 // in occurrence order, which is the element order then).
 // blk (table-segmented sort): the block's table, range and first blocks; its digit
 // offsets are the table's first position plus prefixes within the table, read off the
 // global per-digit scan as differences from the table's first block.
-template <typename K, int ITEMS, bool IDENT, bool FUSED, bool B16>
+template <typename K, int ITEMS, bool IDENT, bool FUSED, bool B16, bool VAL>
 __global__ __launch_bounds__(kThreads) void radix_downsweep_kernel(
     const K* __restrict__ keys_in, const uint32_t* __restrict__ vals_in,
     const uint16_t* __restrict__ bags_in, K* __restrict__ keys_out,
@@ -376,7 +378,7 @@ __global__ __launch_bounds__(kThreads) void radix_downsweep_kernel(
       const int64_t e = tile + (int64_t)wave * 64 * ITEMS + k * 64 + lane;
       valid[k] = e < end;
       key[k] = valid[k] ? keys_in[e] : (K)0;
-      val[k] = valid[k] ? (IDENT ? (uint32_t)e : vals_in[e]) : 0u;
+      val[k] = (VAL && valid[k]) ? (IDENT ? (uint32_t)e : vals_in[e]) : 0u;
       bag[k] = (B16 && valid[k]) ? bags_in[e] : (uint16_t)0;
     }
     for (int d = lane; d < kBuckets; d += 64) sm.wcnt[wave][d] = 0;
@@ -422,7 +424,7 @@ __global__ __launch_bounds__(kThreads) void radix_downsweep_kernel(
         const uint32_t d = (uint32_t)(key[k] >> shift) & mask;
         const uint32_t pos = sm.tstart[d] + sm.wcnt[wave][d] + rank[k];
         sm.keys[pos] = key[k];
-        sm.vals[pos] = val[k];
+        if constexpr (VAL) sm.vals[pos] = val[k];
         if constexpr (B16) sm.bags[pos] = bag[k];
       }
     }
@@ -433,7 +435,7 @@ __global__ __launch_bounds__(kThreads) void radix_downsweep_kernel(
       const uint32_t d = (uint32_t)(kk >> shift) & mask;
       const uint32_t o = sm.run[d] + (uint32_t)q - sm.tstart[d];
       keys_out[o] = kk;
-      vals_out[o] = sm.vals[q];
+      if constexpr (VAL) vals_out[o] = sm.vals[q];
       if constexpr (B16) bags_out[o] = sm.bags[q];
     }
     __syncthreads();
@@ -550,7 +552,7 @@ __global__ __launch_bounds__(kThreads) void unique_finalize_kernel(
     const bool ok = p < n;
     key[j] = ok ? sk[p] : (K)0;
     prev[j] = (ok && p > 0) ? sk[p - 1] : (K)0;
-    occ[j] = ok ? sv[p] : 0u;
+    occ[j] = (ok && sv) ? sv[p] : ~0u;           // no payload: no inverse to scatter
   }
 #pragma unroll
   for (int j = 0; j < kFinRounds; ++j) {
@@ -615,7 +617,7 @@ __global__ __launch_bounds__(kThreads) void unique_finalize_kernel(
         uniq[r] = (int64_t)kk;
         if (seg_offsets) seg_offsets[r] = (int32_t)p;
       }
-      if (occ[j] < (uint64_t)n) inverse[occ[j]] = (int32_t)r;
+      if (inverse && occ[j] < (uint64_t)n) inverse[occ[j]] = (int32_t)r;
       if (sorted_src) {
         uint32_t bg = bag[j];
         if constexpr (B16) {
@@ -693,12 +695,14 @@ void radix_pass(bool first, const K* kin, const uint32_t* vin, const uint16_t* b
                                                        hist, ld);
   const bool fused = nblocks <= kFusedScanBlocks && !blk;
   if (!fused) radix_scan_kernel<<<kBuckets, kThreads, 0, s>>>(hist, nblocks, ld, totals);
-#define CTR_DS(I, FU, B)                                                                   \
-  radix_downsweep_kernel<K, ITEMS, I, FU, B><<<nblocks, kThreads, 0, s>>>(                 \
+#define CTR_DS(I, FU, B, V)                                                                \
+  radix_downsweep_kernel<K, ITEMS, I, FU, B, V><<<nblocks, kThreads, 0, s>>>(              \
       kin, vin, bin, kout, vout, bout, n, shift, nbits, per_block, blk, hist, totals, nblocks, \
       ld)
-#define CTR_DS2(I, FU) \
-  if (bin) CTR_DS(I, FU, true); else CTR_DS(I, FU, false)
+#define CTR_DS2(I, FU)                                              \
+  if (!vout) CTR_DS(I, FU, true, false);                            \
+  else if (bin) CTR_DS(I, FU, true, true);                          \
+  else CTR_DS(I, FU, false, true)
   if (first) {
     if (fused) { CTR_DS2(true, true); } else { CTR_DS2(true, false); }
   } else {
@@ -718,7 +722,8 @@ struct SegPlan {
 };
 
 // bags_a/bags_b (may be null): the 16-bit sample indices, in occurrence order in bags_a,
-// carried along; *sb receives the buffer that holds them in sorted order.
+// carried along; *sb receives the buffer that holds them in sorted order.  vbuf0 == null:
+// no occurrence payload (bags_a is then required), *sv receives null.
 template <typename K, int ITEMS>
 void radix_sort(int key_bits, K* keys_a, K* keys_b, uint32_t* vbuf0, uint32_t* vbuf1,
                 uint16_t* bags_a, uint16_t* bags_b, int64_t n, uint32_t* hist, uint32_t* totals,
@@ -753,7 +758,7 @@ void radix_sort(int key_bits, K* keys_a, K* keys_b, uint32_t* vbuf0, uint32_t* v
   for (int p = 0; p < passes; ++p) {
     const int left = key_bits - shift;
     const int nbits = (left + (passes - p) - 1) / (passes - p);   // spread bits evenly
-    uint32_t* vout = vb[(passes - 1 - p) & 1];                       // last pass -> vbuf0
+    uint32_t* vout = vbuf0 ? vb[(passes - 1 - p) & 1] : nullptr;    // last pass -> vbuf0
     radix_pass<K, ITEMS>(p == 0, kin, vin, bin, kout, vout, bout, n, shift, nbits, per_block,
                          blk, hist, totals, nblocks, s);
     shift += nbits;
@@ -815,7 +820,10 @@ hipError_t unique_impl(const void* ids, bool ids64, int64_t n, const int64_t* of
   // a2: stable LSD radix sort of (key, occurrence) over the live key bits; values ping-pong
   // so that the last pass lands in `perm` when the caller wants it.  The bags stay in
   // occurrence order (w.bags_a) for the finalize.
-  uint32_t* vbuf0 = perm ? reinterpret_cast<uint32_t*>(perm) : w.vals_a;
+  // no occurrence payload when nothing reads it: neither the inverse map nor the permutation
+  // is wanted, and the bags ride along (16-bit)
+  const bool payload = inverse != nullptr || perm != nullptr || !b16;
+  uint32_t* vbuf0 = !payload ? nullptr : perm ? reinterpret_cast<uint32_t*>(perm) : w.vals_a;
   uint32_t* vbuf1 = perm ? w.vals_a : w.vals_b;
   const K* sk;
   const uint32_t* sv;

@@ -224,14 +224,17 @@ def ctr_unique_ids(ids: torch.Tensor, *, offsets: Optional[torch.Tensor] = None,
                    num_tables: int = 0, row_base: Optional[torch.Tensor] = None,
                    total_rows: int = 0, max_table_rows: int = 0, key_modulus: int = 0,
                    want_perm: bool = True,
-                   want_seg: bool = True, workspace: Optional[torch.Tensor] = None,
+                   want_seg: bool = True, want_inverse: bool = True,
+                   workspace: Optional[torch.Tensor] = None,
                    out: Optional[tuple] = None, sorted_src: Optional[torch.Tensor] = None,
                    stream=None, prepare: bool = False
                    ) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor, Optional[torch.Tensor],
                               Optional[torch.Tensor]]:
     """Returns (uniq int64[n], inverse int32[n], num_unique int32[1], perm, seg_offsets);
     only the first num_unique entries of uniq (and num_unique+1 of seg_offsets) are set.
-    ``out`` may supply those five tensors (perm / seg_offsets may be None); ``sorted_src``
+    ``out`` may supply those five tensors (inverse / perm / seg_offsets may be None: the
+    library then leaves them out, and the sort carries no occurrence payload when none of
+    the three is asked for and the bags ride along); ``sorted_src``
     (int32 [n, 4], 16-byte aligned) receives (distinct-row index, bag, key low word, key high
     word) for every sorted position."""
     n = ids.numel()
@@ -240,7 +243,7 @@ def ctr_unique_ids(ids: torch.Tensor, *, offsets: Optional[torch.Tensor] = None,
         uniq, inv, nu, perm, seg = out
     else:
         uniq = torch.empty(max(n, 1), dtype=torch.int64, device=dev)
-        inv = torch.empty(max(n, 1), dtype=torch.int32, device=dev)
+        inv = torch.empty(max(n, 1), dtype=torch.int32, device=dev) if want_inverse else None
         nu = torch.empty(1, dtype=torch.int32, device=dev)
         perm = torch.empty(max(n, 1), dtype=torch.int32, device=dev) if want_perm else None
         seg = torch.empty(n + 1, dtype=torch.int32, device=dev) if want_seg else None
@@ -252,7 +255,8 @@ def ctr_unique_ids(ids: torch.Tensor, *, offsets: Optional[torch.Tensor] = None,
     wsb = ctypes.c_size_t(ws.numel())
     full = args + (_ptr(uniq), _ptr(inv), _ptr(nu), _ptr(perm), _ptr(seg), _ptr(sorted_src),
                    _ptr(ws), ctypes.byref(wsb))
-    res = (uniq[:n], inv[:n], nu, (perm[:n] if perm is not None else None), seg)
+    res = (uniq[:n], (inv[:n] if inv is not None else None), nu,
+           (perm[:n] if perm is not None else None), seg)
     return _run("ctr_unique_ids", full, stream, prepare, res)
 
 

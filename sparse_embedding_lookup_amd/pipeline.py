@@ -37,7 +37,7 @@ class FrontEnd:
     def __init__(self, w: Workload, device="cuda", table: Optional[torch.Tensor] = None,
                  fused: bool = True, keep_grads: bool = False, pipelined: bool = False,
                  rounding: str = "nearest", sr_seed: int = SR_SEED, pad_r: bool = False,
-                 fused_fwd: bool = False):
+                 fused_fwd: bool = False, lean_unique: bool = False):
         """fused: the backward applies the sparse SGD as each row gradient completes
         (ctr_embbag_bwd_sgd); otherwise ctr_embbag_bwd then ctr_sparse_sgd.  keep_grads: also
         keep the per-row gradients in self.row_grads (always kept when not fused).
@@ -51,11 +51,16 @@ class FrontEnd:
         runner, which assumes contiguous R, refuses it).
         fused_fwd: the forward is one call, ctr_embbag_interaction_fwd (pooling into Z and the
         interaction from an on-chip copy of the pooled vectors), instead of ctr_embbag_fwd
-        then ctr_dot_interaction_fwd (pooled-interaction workloads only)."""
+        then ctr_dot_interaction_fwd (pooled-interaction workloads only).
+        lean_unique: the pooled step's unique (Python-driven and native) produces only what
+        its backward reads (distinct rows, their count, sorted_src): no inverse map,
+        permutation or segment offsets, and no occurrence payload through the sort."""
         assert rounding in ("nearest", "stochastic")
         assert rounding == "nearest" or w.dtype in ("bf16", "f16"), \
             "stochastic rounding: bf16 or fp16 tables"
         self.rounding = rounding
+        self.lean_unique = lean_unique
+
         self.sr_seed = sr_seed
         self._sr_k = 0
         self.w = w
@@ -128,7 +133,11 @@ class FrontEnd:
         """Point the unique outputs, and the prepared calls that use them, at set i."""
         for k, v in self._sets[i].items():
             setattr(self, k, v)
-        self._unique_out = (self.uniq, self.inverse, self.num_unique, self.perm, self.seg)
+        # lean_unique (pooled step): the unique fills what the backward reads, not the inverse
+        # map, the permutation or the segment offsets
+        lean = self.lean_unique and self.w.interaction
+        self._unique_out = (self.uniq, None if lean else self.inverse, self.num_unique,
+                            None if lean else self.perm, None if lean else self.seg)
         if len(self._calls) > i:
             for k, v in self._calls[i].items():
                 setattr(self, k, v)
@@ -436,11 +445,17 @@ class FrontEnd:
             d.ws_unique2, d.ws_unique2_bytes = P(self.ws_unique2), self.ws_unique2.numel()
         d.ws_bwd, d.ws_bwd_bytes = P(self.ws_bwd), self.ws_bwd.numel()
         d.ws_pool, d.ws_pool_bytes = P(self.ws_pool), self.ws_pool.numel()
+        # The pooled step's unique produces what its backward reads: the distinct rows, their
+        # count and sorted_src.  The inverse map, the permutation and the segment offsets are
+        # for the batch-matrix step (which pools through the inverse) and for callers that ask.
+        lean = w.interaction and self.lean_unique
         for i in range(3):
             b = self._sets[min(i, len(self._sets) - 1)]
-            d.uniq[i], d.inverse[i] = P(b["uniq"]), P(b["inverse"])
-            d.num_unique[i], d.perm[i] = P(b["num_unique"]), P(b["perm"])
-            d.seg_offsets[i], d.sorted_src[i] = P(b["seg"]), P(b["sorted_src"])
+            d.uniq[i], d.num_unique[i] = P(b["uniq"]), P(b["num_unique"])
+            d.inverse[i] = None if lean else P(b["inverse"])
+            d.perm[i] = None if lean else P(b["perm"])
+            d.seg_offsets[i] = None if lean else P(b["seg"])
+            d.sorted_src[i] = P(b["sorted_src"])
         self._native = d
         self._ev_fork, self._ev_join = torch.cuda.Event(), torch.cuda.Event()
         self._ev_fork.record()          # torch creates the HIP event on its first record

@@ -182,6 +182,40 @@ def test_unique_sorted_src(name, hint):
                                   ou[oi[op]])
 
 
+@pytest.mark.parametrize("name,hint", [("tiny_tables", False), ("small_tables", False),
+                                       ("large_t8_b8192", True), ("criteo_b1024", True),
+                                       ("uneven_tables", True), ("large_t8_b512", False),
+                                       ("large_t8_b512", True)])
+def test_unique_lean_outputs_match_the_full_call(name, hint):
+    """Without inverse, perm and seg_offsets (the pooled step's backward reads sorted_src
+    only) the distinct rows, their count and sorted_src are the full call's, bit for bit,
+    and match the oracle."""
+    ids, kw = UNIQUE_CASES[name]
+    say("unique lean", name, "hint" if hint else "")
+    n = ids.size
+    rb = np.zeros(len(kw["rows"]) + 1, dtype=np.int64)
+    rb[1:] = np.cumsum(kw["rows"])
+    outs = []
+    for lean in (False, True):
+        src = torch.empty((n, 4), dtype=torch.int32, device=DEV)
+        res = ctr.ctr_unique_ids(dev(ids), offsets=dev(kw["offsets"]), batch=kw["batch"],
+                                 num_tables=kw["T"], row_base=dev(rb), total_rows=int(rb[-1]),
+                                 max_table_rows=max(kw["rows"]) if hint else 0,
+                                 want_perm=not lean, want_seg=not lean, want_inverse=not lean,
+                                 sorted_src=src)
+        assert (res[1] is None) == lean
+        outs.append((host(res[0]), host(res[2]), host(src)))
+    (u0, n0, s0), (u1, n1, s1) = outs
+    U = int(n0[0])
+    assert int(n1[0]) == U
+    np.testing.assert_array_equal(u1[:U], u0[:U])
+    np.testing.assert_array_equal(s1, s0)
+    keys = orc.form_keys(ids, kw["offsets"], kw["T"], kw["batch"], rb)
+    ou, oi, op, _ = orc.unique(keys)
+    np.testing.assert_array_equal(u1[:U], ou)
+    np.testing.assert_array_equal(s1[:, 0], oi[op])
+
+
 def test_unique_empty():
     res = ctr.ctr_unique_ids(torch.zeros(0, dtype=torch.int64, device=DEV), key_modulus=10)
     nu, seg = host(res[2]), host(res[4])
@@ -636,6 +670,35 @@ def test_native_step_matches_python_steps(name, schedule):
         assert torch.equal(fa.table, fb.table)
 
 
+@pytest.mark.parametrize("schedule", ["serial", "overlap", "overlap2"])
+@pytest.mark.parametrize("name", ["small_b256", "criteo_b128", "large_t8_b512"])
+def test_native_lean_unique_step_matches_full(name, schedule):
+    """The native pooled step whose unique fills only what the backward reads (no inverse
+    map, permutation or segment offsets; no occurrence payload through the sort) leaves the
+    table, R, dZ, the row gradients and sorted_src bit-identical to steps with the full
+    unique."""
+    w = {"small_b256": lambda: workloads.small(batch=256),
+         "criteo_b128": lambda: workloads.criteo(batch=128),
+         "large_t8_b512": lambda: workloads.large(batch=512, tables=8, rows=400_000)}[name]()
+    say("native lean unique", name, schedule)
+    fa = FrontEnd(w, DEV, keep_grads=True)
+    fb = FrontEnd(w, DEV, keep_grads=True, pipelined=schedule != "serial", lean_unique=True)
+    if schedule != "serial":
+        fb.native_start(deep=schedule == "overlap2")
+    for k in range(3):
+        fa.step()
+        fb.step_native(schedule)
+        torch.cuda.synchronize()
+        U = int(host(fa.num_unique)[0])
+        assert U == int(host(fb.num_unique)[0])
+        np.testing.assert_array_equal(host(fa.uniq)[:U], host(fb.uniq)[:U])
+        np.testing.assert_array_equal(host(fa.sorted_src), host(fb.sorted_src))
+        np.testing.assert_array_equal(host(fa.row_grads)[:U], host(fb.row_grads)[:U])
+        np.testing.assert_array_equal(host(fa.R), host(fb.R))
+        np.testing.assert_array_equal(host(fa.dZ), host(fb.dZ))
+        assert torch.equal(fa.table, fb.table), k
+
+
 @pytest.mark.parametrize("name", ["small_b256", "criteo_b128", "tensornet_b512"])
 def test_native_deep_schedule_matches_serial(name):
     """ctr_step_run_deep (two batches' uniques in flight, three output sets) leaves the table,
@@ -678,8 +741,10 @@ def test_native_step_graph_matches_eager(name, schedule):
     say("native graph", name, schedule)
     pipelined = schedule != "serial"
     K = 4
-    fa = FrontEnd(w, DEV, keep_grads=True, pipelined=True)
-    fb = FrontEnd(w, DEV, keep_grads=True, pipelined=True)
+    # the pooled workload runs the lean unique, as the bench's captured steps do
+    lean = w.interaction
+    fa = FrontEnd(w, DEV, keep_grads=True, pipelined=True, lean_unique=lean)
+    fb = FrontEnd(w, DEV, keep_grads=True, pipelined=True, lean_unique=lean)
     marks = [torch.cuda.Event(enable_timing=True) for _ in range(2 * K)]
     for m in marks:
         m.record()
