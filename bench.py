@@ -95,7 +95,8 @@ def stage_bytes(w, U):
         return {
             "embbag_fwd": n * rb + 8 * n + 8 * (nb + 1) + 4 * nb * d,
             "interaction_fwd": 4 * B * F * d + 4 * B * (d + P),
-            "interaction_bwd": 4 * B * (d + P) + 8 * B * F * d,
+            # dR and Z read, dZ written at its stored width (bf16 for a bf16 backward)
+            "interaction_bwd": 4 * B * (d + P) + (4 + sg) * B * F * d,
             # the pooled step's unique: ids and offsets in; the distinct rows and sorted_src
             # (16 bytes per position, the backward's input) out
             "unique": 8 * n + 8 * (nb + 1) + 16 * n + 8 * U,

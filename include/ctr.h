@@ -298,7 +298,7 @@ int32_t ctr_embbag_interaction_fwd(const void* table, int32_t dtype, int64_t tot
  * dZ: [batch, F, dim] of dz_dtype: CTR_F32, or CTR_BF16 (nearest-even of the fp32 result;
  * needs compute = CTR_BF16).  A bf16 dZ halves the bytes the backward of the pooling re-reads
  * per occurrence; its consumer accumulates in fp32 (ctr_embbag_bwd_sgd with grad_dtype =
- * CTR_BF16).  compute as in the forward (bf16 rounds dP and Z).
+ * CTR_BF16).  compute as in the forward (bf16 rounds dP and Z; Z and dZ 16-byte aligned).
  */
 int32_t ctr_dot_interaction_bwd(const float* Z, const float* dR, int64_t dr_stride,
                                 int64_t batch, int32_t num_vectors, int32_t dim,

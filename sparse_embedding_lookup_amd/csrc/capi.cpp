@@ -520,6 +520,8 @@ static int32_t interaction_bwd_common(const float* Z, const float* dR, int64_t d
   if (batch > 0 && !dR) return fail(CTR_ERR_INVALID_ARGUMENT, "dR is NULL");
   if (dz_bf16 && compute != CTR_BF16)
     return fail(CTR_ERR_UNSUPPORTED, "a bf16 dZ needs compute = CTR_BF16");
+  if (compute == CTR_BF16 && dZ && !aligned16(dZ))
+    return fail(CTR_ERR_UNSUPPORTED, "dZ is not 16-byte aligned");
   return hip_status(ctr::launch_interaction_bwd(Z, dR, dr_stride, batch, F, dim,
                                                 compute == CTR_BF16, pairs, dz_bf16, dZ,
                                                 (hipStream_t)stream),

@@ -50,6 +50,28 @@ __device__ __forceinline__ int tri_row(int q) {
   return i;
 }
 
+// tri_row for q < 2^20 without loops: the single-precision square root is within one unit in
+// the last place, so the estimate is off by at most one row either way.
+__device__ __forceinline__ int tri_row_small(int q) {
+  int i = (int)((1.0f + __builtin_sqrtf(1.0f + 8.0f * (float)q)) * 0.5f);
+  i -= (int)(i * (i - 1) / 2 > q);
+  i += (int)((i + 1) * i / 2 <= q);
+  return i;
+}
+
+// q = i F + j for q < 2^20 and F <= 4096, from a binary32 reciprocal of F: the estimate of i
+// is off by at most one, corrected without branches.
+__device__ __forceinline__ void divmod_small(int q, int F, float rcp, int* i, int* j) {
+  int a = (int)((float)q * rcp);
+  int r = q - a * F;
+  a -= (int)(r < 0);
+  r += r < 0 ? F : 0;
+  a += (int)(r >= F);
+  r -= r >= F ? F : 0;
+  *i = a;
+  *j = r;
+}
+
 __device__ __forceinline__ int tri_index(int i, int j) {
   return i > j ? i * (i - 1) / 2 + j : j * (j - 1) / 2 + i;
 }
@@ -417,111 +439,183 @@ __global__ __launch_bounds__(kThreads) void interaction_fwd_mfma_kernel(
 }
 
 // ------------------------------------------------------------------------- bf16 backward
-// One wave per sample; WPB samples per block; LDS holds each sample's pair gradients, rounded
-// to bf16 once (they are matrix-core operands; doubling a self-dot's entry stays exact), which
-// halves the LDS a block needs.  For each 32-row block of S (A operand, built once from LDS)
-// and each 32-column slab of Z (B operand, re-read per row block from L1/L2), 2*FB MFMAs give
-// a 32x32 block of dZ.
-// OUTB: dZ is stored as bf16 (nearest-even of the fp32 accumulator) instead of fp32.
-template <int FB, int KS, int PS, bool OUTB>
-__global__ __launch_bounds__(kThreads) void interaction_bwd_mfma_kernel(
-    const float* __restrict__ Z, const float* __restrict__ dR, int64_t dr_stride,
-    int64_t batch, int F, int wpb, void* __restrict__ dZ) {
-  constexpr int FKS = 2 * FB;             // k-steps of 16 over the padded F
+// The product is taken transposed, dZ^T = Z^T S (S is symmetric), so that the matrix cores'
+// operands come from where they are cheap:
+// * A = Z^T: a lane holds 8 consecutive rows j of one column of Z (the K index of the
+//   fragment).  Each fragment is loaded once (4-byte loads, 128 bytes per row and
+//   half-wave), rounded to bf16 and kept in registers for every row block of the output.
+// * B = S: the symmetric pair-gradient matrix, rounded to bf16 once and written densely into
+//   LDS (rows of 16 KM + 8 values, so rows 16 lanes apart sit in distinct banks) from
+//   coalesced reads of the pair gradients; a fragment is one 16-byte row segment.
+// A lane's accumulator then holds 4 consecutive columns of one dZ row, stored as one 8-
+// (bf16) or 16-byte (fp32) vector.
+// Work split: a wave per 32-column slab of one sample (NB = dim / 32 waves per sample, at
+// least one), SPB samples per block, the sample's waves building its S together.  Every load
+// of a sample (its Z slab and the first pair gradients) is issued before the first wait.
+// KM: 16-row k-steps covering F.  OUTB: dZ stored as bf16 (nearest-even of the fp32 sum).
+template <int KM>
+__host__ __device__ constexpr int s_pitch() { return 16 * KM + 8; }
+constexpr int kBwdChunk = 16;      // pair gradients per thread in flight at once
+
+// Z rows 16 s + 8 kg .. + 7 of column n (clamped into dim) of one sample: no branch per load
+// (a branch around each load serializes them), the row clamped into the sample; rows past F
+// are zeroed when the fragments are packed.
+template <int KM, int KS>
+__device__ __forceinline__ void bwd_load_slab(const float* zb, int F, int n, int kg,
+                                              float (&x)[KM][8]) {
   constexpr int dim = KS * 16;
-  extern __shared__ __align__(16) unsigned char sp_raw[];
+  const int cn = n < dim ? n : dim - 1;
+#pragma unroll
+  for (int s = 0; s < KM; ++s) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int j = 16 * s + 8 * kg + e;
+      x[s][e] = zb[(j < F ? j : F - 1) * dim + cn];
+    }
+  }
+}
+
+// Pair gradients q0 + c NT + t (c < kBwdChunk) of one sample, as S entries in binary32: the
+// gradient itself, or dG_ij + dG_ji for the Gram matrix.
+template <int PS, int NT>
+__device__ __forceinline__ void bwd_load_pairs(const float* g, int P, int F, float rcpF, int q0,
+                                               int t, float (&v)[kBwdChunk]) {
+#pragma unroll
+  for (int c = 0; c < kBwdChunk; ++c) {
+    const int q = q0 + c * NT + t;
+    const int cq = q < P ? q : P - 1;
+    if constexpr (PS == kGram) {
+      int i, j;
+      divmod_small(cq, F, rcpF, &i, &j);
+      v[c] = g[cq] + g[j * F + i];      // the diagonal: 2 dG_ii
+    } else {
+      v[c] = g[cq];
+    }
+  }
+}
+
+// The same entries written into S (bf16, nearest-even), both triangles.
+template <int PS, int NT, int KM>
+__device__ __forceinline__ void bwd_write_pairs(__bf16* S, int P, int F, float rcpF, int q0,
+                                                int t, const float (&v)[kBwdChunk]) {
+  constexpr int pitch = s_pitch<KM>();
+#pragma unroll
+  for (int c = 0; c < kBwdChunk; ++c) {
+    const int q = q0 + c * NT + t;
+    if (q >= P) break;
+    if constexpr (PS == kGram) {
+      int i, j;
+      divmod_small(q, F, rcpF, &i, &j);
+      S[i * pitch + j] = (__bf16)v[c];
+    } else {
+      const int r = PS == kSelf ? tri_row_small(q) - 1 : tri_row_small(q);
+      const int i = r, j = q - (PS == kSelf ? r * (r + 1) / 2 : r * (r - 1) / 2);
+      const __bf16 h = (__bf16)v[c];
+      if (i != j) {
+        S[i * pitch + j] = h;
+        S[j * pitch + i] = h;
+      } else {
+        // d<z_i, z_i>/dz_i = 2 z_i (doubling a bf16 value is exact)
+        S[i * pitch + i] = (__bf16)(2.0f * (float)h);
+      }
+    }
+  }
+}
+
+template <int KM, int KS, int PS, bool OUTB>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 4)))
+void interaction_bwd_mfma_kernel(
+    const float* __restrict__ Z, const float* __restrict__ dR, int64_t dr_stride,
+    int64_t batch, int F, int spb, void* __restrict__ dZ) {
+  constexpr int dim = KS * 16;
+  constexpr int NB = (dim + 31) / 32;      // 32-column slabs: waves per sample
+  constexpr int NT = NB * 64;              // threads per sample
+  constexpr int FB = (KM + 1) / 2;         // 32-row blocks of dZ
+  constexpr int pitch = s_pitch<KM>();     // bf16 per LDS row of S (an odd multiple of 8)
+  extern __shared__ __align__(16) unsigned char s_raw[];
   const int lane = threadIdx.x & 63;
   const int wv = threadIdx.x >> 6;
+  const int sl = wv / NB;                  // sample within the block
+  const int nb = wv - sl * NB;             // slab
+  const int t = nb * 64 + lane;            // thread within the sample
+  const int rl = lane & 31, kg = lane >> 5;
+  const int n = 32 * nb + rl;              // column of Z (A row) of this lane
+  __bf16* S = reinterpret_cast<__bf16*>(s_raw) + (size_t)sl * F * pitch;
   const int P = num_pairs<PS>(F);
-  const int64_t b = (int64_t)blockIdx.x * wpb + wv;
-  const bool live = wv < wpb && b < batch;
-  // slot P holds 0: the padding (and the diagonal); P + 2 slots keep 4-byte alignment
-  __bf16* sp = reinterpret_cast<__bf16*>(sp_raw) + wv * (P + 2);
+  const float rcpF = 1.0f / (float)F;
+  const int64_t b = (int64_t)blockIdx.x * spb + sl;
+  const bool live = b < batch;
+
+  // S rows 0..F-1, columns 0..16 KM - 1 zeroed first: the strict set's diagonal and the
+  // columns past F stay zero
+  {
+    u32x4* s4 = reinterpret_cast<u32x4*>(S);
+    const int units = F * pitch / 8;
+    const u32x4 zero = {0u, 0u, 0u, 0u};
+    for (int u = t; u < units; u += NT) s4[u] = zero;
+  }
+  __syncthreads();
+
+  // every load of the sample (its Z slab, then the first pair gradients) before any wait; S
+  float x[KM][8] = {};
   if (live) {
     const float* g = dR + b * dr_stride + dim;
-    if constexpr (PS == kGram) {
-      // S itself: dG_ij + dG_ji in binary32, then rounded to bf16 once
-      for (int q = lane; q < P; q += 64) {
-        const int i = q / F, j = q - (q / F) * F;
-        sp[q] = (__bf16)(g[i * F + j] + g[j * F + i]);
-      }
-    } else {
-      for (int q = lane; q < P; q += 64) sp[q] = (__bf16)g[q];
+    float v[kBwdChunk];
+    bwd_load_slab<KM, KS>(Z + b * (int64_t)F * dim, F, n, kg, x);
+    bwd_load_pairs<PS, NT>(g, P, F, rcpF, 0, t, v);
+    bwd_write_pairs<PS, NT, KM>(S, P, F, rcpF, 0, t, v);
+    for (int q0 = kBwdChunk * NT; q0 < P; q0 += kBwdChunk * NT) {
+      bwd_load_pairs<PS, NT>(g, P, F, rcpF, q0, t, v);
+      bwd_write_pairs<PS, NT, KM>(S, P, F, rcpF, q0, t, v);
     }
-    if (lane == 0) sp[P] = (__bf16)0.f;
+  }
+  // the A fragments, rows past F zeroed here rather than at the loads (a mask right after each
+  // load would make the wave wait for it before the pair gradients' loads are issued)
+  bf16x8 zf[KM];
+#pragma unroll
+  for (int s = 0; s < KM; ++s) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      if (16 * s + 8 * kg + e >= F) x[s][e] = 0.f;
+    zf[s] = pack_bf16x8(x[s]);
   }
   __syncthreads();
   if (!live) return;
-  const float* zb = Z + b * (int64_t)F * dim;
-  const int rl = lane & 31, kg = lane >> 5;
-  const int kmax = (F + 15) / 16;          // k-steps holding any row j < F
 
-  constexpr int nblk = (dim + 31) / 32;
-#pragma unroll 1
+#pragma unroll
   for (int I = 0; I < FB; ++I) {
     if (32 * I >= F) break;
-    const int i = 32 * I + rl;
-    // A fragments of S for this row block, built once from the pair gradients in LDS
-    // Index arithmetic without compare masks: an invalid (i, j) (diagonal, or outside F)
-    // reads the zero slot P.
-    // (kgx is kg through an opaque zero, so j-dependent terms are not hoisted out of the
-    // loops and kept live across them)
-    const int vi = (int)((unsigned)(i - F) >> 31);             // 1 if i < F
-    const int kgx = kg + pinned_zero();
-    bf16x8 af[FKS];
+    const int i = 32 * I + rl;               // output row (B column); rows past F not stored
+    const int ci = i < F ? i : F - 1;
+    f32x16 acc;
 #pragma unroll
-    for (int s = 0; s < FKS; ++s) {
+    for (int r = 0; r < 16; ++r) acc[r] = 0.f;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int j = 16 * s + 8 * kgx + e;
-        const int vj = (int)((unsigned)(j - F) >> 31);           // 1 if j < F
-        const int ne = (int)((0u - (unsigned)(i ^ j)) >> 31);    // 1 if i != j
-        const int ok = vi & vj & (PS != kStrict ? 1 : ne);
-        const int q = ok * (PS == kGram   ? i * F + j
-                            : PS == kSelf ? sym_pair_index<kSelf>(i, j)
-                                          : tri_index(i, j)) +
-                      (1 - ok) * P;
-        // d<z_i, z_i>/dz_i = 2 z_i: the diagonal of S carries twice the self-dot gradient
-        // (the Gram matrix's S already holds dG_ii + dG_ii)
-        af[s][e] = PS == kSelf ? (__bf16)((float)sp[q] * (float)(2 - ne)) : sp[q];
-      }
+    for (int s = 0; s < KM; ++s) {
+      const bf16x8 sf = *reinterpret_cast<const bf16x8*>(S + ci * pitch + 16 * s + 8 * kg);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(zf[s], sf, acc, 0, 0, 0);
     }
-#pragma unroll 1
-    for (int nb = 0; nb < nblk; ++nb) {
-      const int n = 32 * nb + rl;
-      const bool nvalid = n < dim;
-      const int kgy = kg + pinned_zero();
-      const float* zp = zb + pinned_zero();
-      f32x16 acc;
+    if (i >= F) continue;
+    // acc[4 u + e] = dZ[i][32 nb + 8 u + 4 kg + e]
 #pragma unroll
-      for (int v = 0; v < 16; ++v) acc[v] = 0.f;
+    for (int u = 0; u < 4; ++u) {
+      const int c0 = 32 * nb + 8 * u + 4 * kg;
+      if (c0 >= dim) continue;
+      float val[4];
 #pragma unroll
-      for (int s = 0; s < FKS; ++s) {
-        if (s >= kmax) break;
-        float x[8];
-        const int cn = nvalid ? n : dim - 1;
+      for (int e = 0; e < 4; ++e) val[e] = acc[4 * u + e];
+      if (i == 0) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int j = 16 * s + 8 * kgy + e;
-          const unsigned vj = (unsigned)(j - F) >> 31;           // 1 if j < F
-          const int cj = (int)vj * j + (1 - (int)vj) * (F - 1);  // clamped row
-          const unsigned keep = 0u - (vj & (unsigned)nvalid);    // all ones or zero
-          x[e] = __uint_as_float(__float_as_uint(zp[cj * dim + cn]) & keep);
-        }
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[s], pack_bf16x8(x), acc, 0, 0, 0);
+        for (int e = 0; e < 4; ++e) val[e] += dR[b * dr_stride + c0 + e];
       }
-      if (!nvalid) continue;
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int io = 32 * I + 8 * (v >> 2) + 4 * kg + (v & 3);
-        if (io < F) {
-          float val = acc[v];
-          if (io == 0) val += dR[b * dr_stride + n];
-          if constexpr (OUTB)
-            static_cast<__bf16*>(dZ)[(b * F + io) * dim + n] = (__bf16)val;
-          else
-            static_cast<float*>(dZ)[(b * F + io) * dim + n] = val;
-        }
+      const int64_t o = (b * F + i) * dim + c0;
+      if constexpr (OUTB) {
+        typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+        const bf16x4 w = {(__bf16)val[0], (__bf16)val[1], (__bf16)val[2], (__bf16)val[3]};
+        *reinterpret_cast<bf16x4*>(static_cast<__bf16*>(dZ) + o) = w;
+      } else {
+        const float4 w = {val[0], val[1], val[2], val[3]};
+        *reinterpret_cast<float4*>(static_cast<float*>(dZ) + o) = w;
       }
     }
   }
@@ -620,8 +714,9 @@ bool interaction_bf16_supported(int F, int dim, int pairs) {
   const int FB = (F + 31) / 32, KS = dim / 16;
   if (!(KS == 1 || KS == 2 || KS == 4 || KS == 8)) return false;
   if (FB * KS > 32) return false;                       // register budget of the forward
-  // one wave's bf16 gradients in LDS
-  return ((size_t)num_pairs_of(pairs, F) + 2) * 2 <= 65536;
+  // one wave's dense bf16 gradient matrix in LDS (the backward)
+  (void)pairs;
+  return (size_t)F * (16 * ((F + 15) / 16) + 8) * 2 <= 65536;
 }
 
 bool interaction_f32_supported(int F, int dim, int pairs) {
@@ -704,30 +799,46 @@ hipError_t interaction_bwd(const float* Z, const float* dR, int64_t dr_stride, i
                                                                            batch, F, dim, spb, dZ);
     return hipGetLastError();
   }
-  const int FB = (F + 31) / 32;
-  int wpb = 65536 / ((P + 2) * 2);
-  if (wpb > 4) wpb = 4;
-  if (wpb < 1) wpb = 1;
-  const size_t lds = (size_t)wpb * (P + 2) * sizeof(__bf16);
-  const int64_t blocks = (batch + wpb - 1) / wpb;
+  const int KM = (F + 15) / 16;
+  // a wave per 32-column slab; samples per block: as many as fit 4 waves and 64 KiB of LDS
+  const int NB = (dim + 31) / 32;
+  const int row_bytes = (16 * KM + 8) * (int)sizeof(__bf16);
+  int spb = 65536 / (F * row_bytes);
+  if (spb > 4 / NB) spb = 4 / NB;
+  if (spb < 1) spb = 1;
+  const size_t lds = (size_t)spb * F * row_bytes;
+  const int64_t blocks = (batch + spb - 1) / spb;
+  const unsigned threads = (unsigned)(spb * NB * 64);
   const int KS = dim / 16;
-#define CTR_BWD_MFMA(KS_)                                                                      \
+#define CTR_BWD_MFMA_KS(KM_, KS_)                                                              \
   do {                                                                                         \
     if (out_bf16)                                                                              \
-      interaction_bwd_mfma_kernel<FB, KS_, PS, true><<<(unsigned)blocks, kThreads, lds, s>>>( \
-          Z, dR, dr_stride, batch, F, wpb, dZv);                                               \
+      interaction_bwd_mfma_kernel<KM_, KS_, PS, true><<<(unsigned)blocks, threads, lds, s>>>(  \
+          Z, dR, dr_stride, batch, F, spb, dZv);                                               \
     else                                                                                       \
-      interaction_bwd_mfma_kernel<FB, KS_, PS, false><<<(unsigned)blocks, kThreads, lds, s>>>( \
-          Z, dR, dr_stride, batch, F, wpb, dZv);                                               \
+      interaction_bwd_mfma_kernel<KM_, KS_, PS, false><<<(unsigned)blocks, threads, lds, s>>>( \
+          Z, dR, dr_stride, batch, F, spb, dZv);                                               \
   } while (0)
-  CTR_FB_DISPATCH(FB, {
-    switch (KS) {
-      case 1: CTR_BWD_MFMA(1); break;
-      case 2: CTR_BWD_MFMA(2); break;
-      case 4: CTR_BWD_MFMA(4); break;
-      default: CTR_BWD_MFMA(8); break;
-    }
-  });
+#define CTR_BWD_MFMA(KM_)                            \
+  do {                                               \
+    switch (KS) {                                    \
+      case 1: CTR_BWD_MFMA_KS(KM_, 1); break;        \
+      case 2: CTR_BWD_MFMA_KS(KM_, 2); break;        \
+      case 4: CTR_BWD_MFMA_KS(KM_, 4); break;        \
+      default: CTR_BWD_MFMA_KS(KM_, 8); break;       \
+    }                                                \
+  } while (0)
+  switch (KM) {
+    case 1: CTR_BWD_MFMA(1); break;
+    case 2: CTR_BWD_MFMA(2); break;
+    case 3: CTR_BWD_MFMA(3); break;
+    case 4: CTR_BWD_MFMA(4); break;
+    case 5: CTR_BWD_MFMA(5); break;
+    case 6: CTR_BWD_MFMA(6); break;
+    case 7: CTR_BWD_MFMA(7); break;
+    default: CTR_BWD_MFMA(8); break;
+  }
+#undef CTR_BWD_MFMA_KS
 #undef CTR_BWD_MFMA
   return hipGetLastError();
 }

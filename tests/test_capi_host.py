@@ -201,6 +201,10 @@ def test_interaction_bad_args():
     assert b(FAKE, FAKE, 26, 10, 5, 16, 1, 7, FAKE, None) == ctr.CTR_ERR_INVALID_ARGUMENT
     assert b"dz_dtype" in lib.ctr_last_error_message()
     assert b(FAKE, FAKE, 26, 10, 5, 16, 0, 1, FAKE, None) == ctr.CTR_ERR_UNSUPPORTED
+    # the matrix-core backward stores dZ as 8- and 16-byte vectors
+    assert b(FAKE, FAKE, 26, 10, 5, 16, 1, 1, MISALIGNED, None) == ctr.CTR_ERR_UNSUPPORTED
+    assert b"dZ is not 16-byte aligned" in lib.ctr_last_error_message()
+    assert b(FAKE, FAKE, 26, 10, 5, 16, 1, 0, MISALIGNED, None) == ctr.CTR_ERR_UNSUPPORTED
 
 
 def test_sgd_gather_init_validate_bad_args():
