@@ -29,7 +29,8 @@ constexpr int kThreads = 256;
 // summed, never on where the sums go: with or without the update, the same gradients give
 // the same row sums bit for bit.  fp32 gradient rows (16 bytes per lane) run best at 4,
 // packed bf16 rows at 6 (measured on the Small, TensorNet, Criteo-shaped and Large
-// workloads).  The workspace is sized for the smallest depth.
+// workloads; with 8-column lanes, 4 and 8 were slower on Criteo and Large too).  The
+// workspace is sized for the smallest depth.
 template <bool GB>
 constexpr int slot_depth() { return GB ? 6 : 4; }
 constexpr int kMinSlotDepth = 4;
@@ -107,6 +108,7 @@ using L0Source = L0SourceT<false>;
 using L0SourceB = L0SourceT<true>;
 
 struct LnSource {
+  static constexpr bool kBf16 = false;
   const int32_t* keys;
   const float* rows;
   int dim;
@@ -220,33 +222,108 @@ __device__ __forceinline__ void store_updated(const SgdTarget& sgd, int64_t key,
   }
 }
 
-// The table row a slot holds for the piece it may finish after the chunk's join.
-template <int MODE>
-struct PendingRow {
-  int64_t key = -1;
-  WVec<MODE> w;
+// CW columns of a table row (4, or 8 for the bf16 gradient rows' 8-column lanes): read, and
+// written back as W - lr * g with the same arithmetic and rounding as four columns at a time.
+template <int MODE, int CW>
+struct TRow {
+  WVec<MODE> v[CW / 4];
+};
+template <int MODE, int CW>
+__device__ __forceinline__ TRow<MODE, CW> load_trow(const SgdTarget& sgd, int64_t key, int c,
+                                                    bool ok) {
+  TRow<MODE, CW> r;
+  if constexpr (CW == 8 && MODE >= 2) {
+    const uint4 q = ok ? *reinterpret_cast<const uint4*>(sgd.table + key * sgd.row_bytes +
+                                                         (int64_t)c * 2)
+                       : make_uint4(0u, 0u, 0u, 0u);
+    r.v[0] = make_uint2(q.x, q.y);
+    r.v[1] = make_uint2(q.z, q.w);
+  } else {
+#pragma unroll
+    for (int a = 0; a < CW / 4; ++a) r.v[a] = load_wvec<MODE>(sgd, key, c + 4 * a, ok);
+  }
+  return r;
+}
+template <int MODE, int CW>
+__device__ __forceinline__ void store_trow(const SgdTarget& sgd, int64_t key, int c,
+                                           const float* g, const TRow<MODE, CW>& w) {
+  if constexpr (CW == 8 && MODE >= 2) {
+    const uint2 lo = half_updated<MODE>(sgd, key, c, g[0], g[1], g[2], g[3], w.v[0]);
+    const uint2 hi = half_updated<MODE>(sgd, key, c + 4, g[4], g[5], g[6], g[7], w.v[1]);
+    *reinterpret_cast<uint4*>(sgd.table + key * sgd.row_bytes + (int64_t)c * 2) =
+        make_uint4(lo.x, lo.y, hi.x, hi.y);
+  } else {
+#pragma unroll
+    for (int a = 0; a < CW / 4; ++a)
+      store_updated<MODE>(sgd, key, c + 4 * a,
+                          make_float4(g[4 * a], g[4 * a + 1], g[4 * a + 2], g[4 * a + 3]),
+                          w.v[a]);
+  }
+}
+
+// CW gradient values of one lane: 4 (one 16-byte fp32 or 8-byte bf16 vector), or 8 bf16 in
+// one 16-byte vector.
+template <typename Src, int CW>
+struct GVec {
+  using T = typename Src::Raw;
+  static __device__ __forceinline__ T load(const Src& S, int64_t off) { return S.load_raw(off); }
+  static __device__ __forceinline__ T zero() { return Src::zero_raw(); }
+  static __device__ __forceinline__ void widen(const T& r, float* x) {
+    const float4 f = Src::widen(r);
+    x[0] = f.x; x[1] = f.y; x[2] = f.z; x[3] = f.w;
+  }
+};
+template <typename Src>
+struct GVec<Src, 8> {
+  static_assert(Src::kBf16, "8-column lanes take bf16 gradient rows");
+  using T = uint4;
+  static __device__ __forceinline__ T load(const Src& S, int64_t off) {
+    return *reinterpret_cast<const uint4*>(static_cast<const __bf16*>(S.grad) + off);
+  }
+  static __device__ __forceinline__ T zero() { return make_uint4(0u, 0u, 0u, 0u); }
+  static __device__ __forceinline__ void widen(const T& r, float* x) {
+    x[0] = bf16_lo(r.x); x[1] = bf16_hi(r.x); x[2] = bf16_lo(r.y); x[3] = bf16_hi(r.y);
+    x[4] = bf16_lo(r.z); x[5] = bf16_hi(r.z); x[6] = bf16_lo(r.w); x[7] = bf16_hi(r.w);
+  }
 };
 
-// Sum the slot's KPS sorted positions when one 16-byte vector per lane covers a row
-// (d <= 4G).  Each sorted position carries (u, bag, table row), so the slot issues every
+// The table row a slot holds for the piece it may finish after the chunk's join.
+template <int MODE, int CW>
+struct PendingRow {
+  int64_t key = -1;
+  TRow<MODE, CW> w;
+};
+
+// Sum the slot's KPS sorted positions when one vector of CW columns per lane covers a row
+// (d <= CW G): CW = 4, or 8 for bf16 gradient rows (16 bytes per lane, so a wave covers
+// twice the rows and each position's bookkeeping is shared by twice the bytes).  Each sorted
+// position carries (u, bag, table row), so the slot issues every
 // memory access it needs in two dependent rounds: its entries, then all gradient rows
 // together with the table rows of the segments it completes (and of its last piece, which
 // it may complete after the chunk's join).  A position ends a piece where the next key
 // differs; a piece whose key equals the key just before the slot began earlier (sorted
 // keys), and one whose key equals the key just after continues later: those two go to LDS
 // for the join, every other piece is complete and is written out (and applied) here.
-template <int G, int MODE, int KPS, typename Src>
+template <int G, int CW, int MODE, int KPS, typename Src>
 __device__ __forceinline__ void slot_prefetched(const Src& S, int64_t q0, int64_t q1,
                                                 int64_t n, int dim, int64_t capacity,
                                                 float* __restrict__ row_grads,
-                                                const SgdTarget& sgd, SegSmem<G, 1>& sm, int slot,
-                                                int lane, int32_t& fkey, int32_t& fcont,
-                                                int32_t& lkey, PendingRow<MODE>& pend) {
+                                                const SgdTarget& sgd, SegSmem<G, CW / 4>& sm,
+                                                int slot, int lane, int32_t& fkey, int32_t& fcont,
+                                                int32_t& lkey, PendingRow<MODE, CW>& pend) {
+  using GV = GVec<Src, CW>;
   constexpr int kRegs = (KPS + G - 1) / G;
   const int lane0 = (threadIdx.x & 63) & ~(G - 1);
   const int len = (int)(q1 - q0);
-  const int c = lane * 4;
+  const int c = lane * CW;
   const bool col_ok = c < dim;
+  // the lane's CW sums into LDS (the join's first / last pieces)
+  auto to_lds = [&](float* row, const float* v) {
+#pragma unroll
+    for (int a = 0; a < CW / 4; ++a)
+      *reinterpret_cast<float4*>(row + c + 4 * a) =
+          make_float4(v[4 * a], v[4 * a + 1], v[4 * a + 2], v[4 * a + 3]);
+  };
 
   // (u, bag, row) of position e = r*G + lane in register r
   int32_t ekey[kRegs];
@@ -270,7 +347,7 @@ __device__ __forceinline__ void slot_prefetched(const Src& S, int64_t q0, int64_
 
   // all gradient rows of the slot
   int32_t kk[KPS];
-  typename Src::Raw rv[KPS];
+  typename GV::T rv[KPS];
 #pragma unroll
   for (int e = 0; e < KPS; ++e) {
     kk[e] = __shfl(ekey[e / G], lane0 + (e % G), 64);
@@ -278,12 +355,12 @@ __device__ __forceinline__ void slot_prefetched(const Src& S, int64_t q0, int64_
     if ((int64_t)bag >= S.num_bags) bag = 0;
     const uint32_t t = bag / (uint32_t)S.batch, b = bag - t * (uint32_t)S.batch;
     const int64_t goff = (int64_t)b * S.sb + (int64_t)t * S.st;
-    rv[e] = (e < len && col_ok && kk[e] != -1) ? S.load_raw(goff + c) : Src::zero_raw();
+    rv[e] = (e < len && col_ok && kk[e] != -1) ? GV::load(S, goff + c) : GV::zero();
   }
 
   // table rows of the segments completed inside the slot, and of the last piece
   int64_t rk[kRegs];
-  WVec<MODE> w[KPS];
+  TRow<MODE, CW> w[KPS];
   if constexpr (MODE != 0) {
 #pragma unroll
     for (int r = 0; r < kRegs; ++r) {
@@ -304,43 +381,49 @@ __device__ __forceinline__ void slot_prefetched(const Src& S, int64_t q0, int64_
 #pragma unroll
     for (int e = 0; e < KPS; ++e) {
       const int64_t key = __shfl(rk[e / G], lane0 + (e % G), 64);
-      w[e] = load_wvec<MODE>(sgd, key, c, key >= 0 && col_ok);
+      w[e] = load_trow<MODE, CW>(sgd, key, c, key >= 0 && col_ok);
     }
   }
 
-  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  float acc[CW];
+#pragma unroll
+  for (int i = 0; i < CW; ++i) acc[i] = 0.f;
 #pragma unroll
   for (int e = 0; e < KPS; ++e) {
     if (e < len) {
-      const float4 x = Src::widen(rv[e]);
-      acc.x += x.x;
-      acc.y += x.y;
-      acc.z += x.z;
-      acc.w += x.w;
+      float x[CW];
+      GV::widen(rv[e], x);
+#pragma unroll
+      for (int i = 0; i < CW; ++i) acc[i] += x[i];
       const int32_t k = kk[e];
       const int32_t nx = (e + 1 < len) ? kk[e + 1 < KPS ? e + 1 : e] : ka;
       if (nx != k) {                           // the piece ends at e
         if (k == kb) {                         // ... and began before the slot
           fkey = k;
           fcont = 0;
-          *reinterpret_cast<float4*>(&sm.first_row[slot][c]) = acc;
+          to_lds(sm.first_row[slot], acc);
         } else if (k >= 0 && (int64_t)k < capacity) {
-          if (row_grads && col_ok)
-            *reinterpret_cast<float4*>(row_grads + (int64_t)k * dim + c) = acc;
+          if (row_grads && col_ok) {
+#pragma unroll
+            for (int a = 0; a < CW / 4; ++a)
+              *reinterpret_cast<float4*>(row_grads + (int64_t)k * dim + c + 4 * a) =
+                  make_float4(acc[4 * a], acc[4 * a + 1], acc[4 * a + 2], acc[4 * a + 3]);
+          }
           if constexpr (MODE != 0) {
             const int64_t key = __shfl(rk[e / G], lane0 + (e % G), 64);
-            if (key >= 0 && col_ok) store_updated<MODE>(sgd, key, c, acc, w[e]);
+            if (key >= 0 && col_ok) store_trow<MODE, CW>(sgd, key, c, acc, w[e]);
           }
         }
-        acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+        for (int i = 0; i < CW; ++i) acc[i] = 0.f;
       } else if (e == len - 1) {               // still open at the slot's end: continues
         if (k == kb) {
           fkey = k;
           fcont = 1;
-          *reinterpret_cast<float4*>(&sm.first_row[slot][c]) = acc;
+          to_lds(sm.first_row[slot], acc);
         } else {
           lkey = k;
-          *reinterpret_cast<float4*>(&sm.last_row[slot][c]) = acc;
+          to_lds(sm.last_row[slot], acc);
           if constexpr (MODE != 0) {
             pend.key = __shfl(rk[e / G], lane0 + (e % G), 64);
             pend.w = w[e];
@@ -354,7 +437,9 @@ __device__ __forceinline__ void slot_prefetched(const Src& S, int64_t q0, int64_
 // One chunk of a reduce-by-key level.  L0: entries are sorted positions of the occurrences
 // (keys from src, rows gathered from grad); otherwise entries are carries (keys may be -1 =
 // empty).  The chunk's at most two carries go to out_keys / out_rows[2 * chunk + {0, 1}].
-template <bool L0, int G, int VPL, int MODE, int KPS, typename Src>
+// W8 (level 0, bf16 gradient rows, VPL = 2): the lanes take 8 adjacent columns each (the
+// prefetched slot with CW = 8); otherwise vector a of a lane holds columns (a G + lane) 4 ...
+template <bool L0, bool W8, int G, int VPL, int MODE, int KPS, typename Src>
 __device__ __forceinline__ void reduce_chunk(
     SegSmem<G, VPL>& sm, Src S, int64_t n, int64_t chunk_id, int dim, int64_t capacity,
     float* __restrict__ row_grads, const SgdTarget& sgd, int32_t* __restrict__ out_keys,
@@ -368,8 +453,11 @@ __device__ __forceinline__ void reduce_chunk(
   const int64_t q1 = q0 + KPS < n ? q0 + KPS : n;
   const int64_t chunk1 = chunk0 + (int64_t)kSlots * KPS < n ? chunk0 + (int64_t)kSlots * KPS : n;
 
+  static_assert(!W8 || (L0 && VPL == 2 && Src::kBf16), "8-column lanes: level 0, bf16 rows");
+  constexpr bool kPrefetched = L0 && (VPL == 1 || W8);
+  constexpr int CW = W8 ? 8 : 4;
   // column of vector a of this lane
-  auto col = [&](int a) { return (a * G + lane) * 4; };
+  auto col = [&](int a) { return W8 ? lane * 8 + 4 * a : (a * G + lane) * 4; };
   auto write_row = [&](float* dst, const RowAcc<VPL>& r) {
 #pragma unroll
     for (int a = 0; a < VPL; ++a) {
@@ -406,12 +494,11 @@ __device__ __forceinline__ void reduce_chunk(
   };
 
   int32_t fkey = -1, fcont = 0, lkey = -1;
-  PendingRow<MODE> pend;
-  if constexpr (L0 && VPL == 1) {
+  PendingRow<MODE, CW> pend;
+  if constexpr (kPrefetched) {
     if (q0 < n)
-      slot_prefetched<G, MODE, KPS, Src>(S, q0, q1, n, dim, capacity, row_grads, sgd, sm, slot,
-                                         lane,
-                               fkey, fcont, lkey, pend);
+      slot_prefetched<G, CW, MODE, KPS, Src>(S, q0, q1, n, dim, capacity, row_grads, sgd, sm,
+                                             slot, lane, fkey, fcont, lkey, pend);
   } else if (q0 < n) {
     // Prefetch the slot's entries cooperatively: entry e is loaded by lane e % G of the slot
     // into register e / G, then broadcast with shuffles.
@@ -578,14 +665,18 @@ __device__ __forceinline__ void reduce_chunk(
       acc.v[a][0] = x.x; acc.v[a][1] = x.y; acc.v[a][2] = x.z; acc.v[a][3] = x.w;
     }
     if (walk(u, slot + 1, acc)) {
-      if constexpr (L0 && VPL == 1) {
+      if constexpr (kPrefetched) {
         // the row was read before the join
         if (u >= 0 && (int64_t)u < capacity) {
           const int c = col(0);
-          const float4 g = make_float4(acc.v[0][0], acc.v[0][1], acc.v[0][2], acc.v[0][3]);
-          if (row_grads && c < dim) *reinterpret_cast<float4*>(row_grads + (int64_t)u * dim + c) = g;
+          float g[CW];
+#pragma unroll
+          for (int a = 0; a < VPL; ++a)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) g[4 * a + i] = acc.v[a][i];
+          if (row_grads && c < dim) write_row(row_grads + (int64_t)u * dim, acc);
           if constexpr (MODE != 0)
-            if (pend.key >= 0 && c < dim) store_updated<MODE>(sgd, pend.key, c, g, pend.w);
+            if (pend.key >= 0 && c < dim) store_trow<MODE, CW>(sgd, pend.key, c, g, pend.w);
         }
       } else {
         emit_complete(u, acc);
@@ -608,7 +699,7 @@ __device__ __forceinline__ void reduce_chunk(
 // level (its writes published by a device-scope fence before the ticket; the finisher
 // fences again before it reads them), which saves a launch.  The L0 kernel, which always
 // precedes, zeroes the ticket.
-template <bool L0, int G, int VPL, int MODE, int KPS, typename Src>
+template <bool L0, bool W8, int G, int VPL, int MODE, int KPS, typename Src>
 __global__ __launch_bounds__(kThreads) void segreduce_kernel(
     Src S, int64_t n, int dim, int64_t capacity, float* __restrict__ row_grads, SgdTarget sgd,
     int32_t* __restrict__ out_keys, float* __restrict__ out_rows, uint32_t* __restrict__ ticket,
@@ -618,8 +709,8 @@ __global__ __launch_bounds__(kThreads) void segreduce_kernel(
   if constexpr (L0) {
     if (ticket && blockIdx.x == 0 && threadIdx.x == 0) *ticket = 0u;
   }
-  reduce_chunk<L0, G, VPL, MODE, KPS, Src>(sm, S, n, (int64_t)blockIdx.x, dim, capacity, row_grads,
-                                      sgd, out_keys, out_rows);
+  reduce_chunk<L0, W8, G, VPL, MODE, KPS, Src>(sm, S, n, (int64_t)blockIdx.x, dim, capacity,
+                                               row_grads, sgd, out_keys, out_rows);
   if constexpr (!L0) {
     if (ticket) {
       __syncthreads();
@@ -631,7 +722,7 @@ __global__ __launch_bounds__(kThreads) void segreduce_kernel(
       if (finisher) {
         __threadfence();
         const LnSource fin{out_keys, out_rows, dim};
-        reduce_chunk<false, G, VPL, MODE, KPS, LnSource>(sm, fin, 2 * (int64_t)gridDim.x, 0, dim,
+        reduce_chunk<false, false, G, VPL, MODE, KPS, LnSource>(sm, fin, 2 * (int64_t)gridDim.x, 0, dim,
                                                     capacity, row_grads, sgd, nullptr,
                                                     spare_rows);
       }
@@ -649,6 +740,16 @@ struct BwdWs {
   float* crows[2];
   size_t bytes;
 };
+
+// Lanes per row of level 0 when bf16 gradient rows are read 8 columns (16 bytes) per lane:
+// the power of two covering dim / 8 (at most 64), or 0 where that does not apply (fp32
+// gradient rows, dim not a multiple of 8, or rows of more than 512 values).
+int level0_w8_lanes(bool bf16_grads, int dim) {
+  if (!bf16_grads || dim % 8 != 0 || dim / 8 > 64) return 0;
+  int G = 1;
+  while (G < dim / 8) G <<= 1;
+  return G;
+}
 
 int64_t chunk_positions(int dim, int kps) {
   const RowGeom rg = row_geom(dim / 4);
@@ -762,21 +863,38 @@ static hipError_t segreduce_levels(const L0S& s0, int64_t nnz, int dim, float* r
   const RowGeom rg = row_geom(dim / 4);
   constexpr int KPS = slot_depth<L0S::kBf16>();
   const int64_t chunk = chunk_positions(dim, KPS);
+  // level 0: bf16 gradient rows in 8-column lanes where the row allows (level0_lanes)
+  const int g8 = level0_w8_lanes(L0S::kBf16, dim);
+  const int64_t chunk0 = g8 ? (int64_t)(kThreads / g8) * KPS : chunk;
+  int64_t blocks = (nnz + chunk0 - 1) / chunk0;
+  int cur = 0;
+  if constexpr (L0S::kBf16) {
+    if (g8) {
+      CTR_SEG_DISPATCH(g8, 1, {
+        (void)VPL;
+        segreduce_kernel<true, true, G, 2, MODE, KPS, L0S><<<(unsigned)blocks, kThreads, 0, s>>>(
+            s0, nnz, dim, nnz, row_grads, sgd, blocks > 1 ? w.ckeys[cur] : nullptr, w.crows[cur],
+            w.ticket, nullptr);
+      });
+    }
+  }
+  if (!g8) {
+    CTR_SEG_DISPATCH(rg.G, rg.VPL, {
+      segreduce_kernel<true, false, G, VPL, MODE, KPS, L0S><<<(unsigned)blocks, kThreads, 0, s>>>(
+          s0, nnz, dim, nnz, row_grads, sgd, blocks > 1 ? w.ckeys[cur] : nullptr, w.crows[cur],
+          w.ticket, nullptr);
+    });
+  }
+  e = record_mark(l0_end, s);
   CTR_SEG_DISPATCH(rg.G, rg.VPL, {
     int64_t len = nnz;
-    int64_t blocks = (len + chunk - 1) / chunk;
-    int cur = 0;
-    segreduce_kernel<true, G, VPL, MODE, KPS, L0S><<<(unsigned)blocks, kThreads, 0, s>>>(
-        s0, len, dim, nnz, row_grads, sgd, blocks > 1 ? w.ckeys[cur] : nullptr, w.crows[cur],
-        w.ticket, nullptr);
-    e = record_mark(l0_end, s);
     while (e == hipSuccess && blocks > 1) {
       len = 2 * blocks;
       blocks = (len + chunk - 1) / chunk;
       LnSource sn{w.ckeys[cur], w.crows[cur], dim};
       // a level whose carries fit one chunk finishes the tree itself
       const bool fold = blocks > 1 && 2 * blocks <= chunk && blocks <= kFoldBlocks;
-      segreduce_kernel<false, G, VPL, MODE, KPS, LnSource><<<(unsigned)blocks, kThreads, 0, s>>>(
+      segreduce_kernel<false, false, G, VPL, MODE, KPS, LnSource><<<(unsigned)blocks, kThreads, 0, s>>>(
           sn, len, dim, nnz, row_grads, sgd, blocks > 1 ? w.ckeys[cur ^ 1] : nullptr,
           w.crows[cur ^ 1], fold ? w.ticket : nullptr, w.crows[cur]);
       cur ^= 1;

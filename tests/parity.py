@@ -58,20 +58,27 @@ def segreduce_depth(n, dim, bf16_grads):
     a slot (KPS - 1 additions), then joins at most (slots - 1) following pieces of the same
     row in order; the carries of a level form the next level's input, until one chunk of
     slots * KPS positions is left.  slots = 256 / G with G = 16-byte vectors per row rounded
-    up to a power of two (at most 64); KPS = 6 for bf16 gradient rows, 4 for fp32."""
+    up to a power of two (at most 64): 4 fp32 values per vector, and at level 0 8 bf16
+    gradient values per vector (when dim is a multiple of 8 and at most 512); KPS = 6 for
+    bf16 gradient rows, 4 for fp32."""
+    def pow2_lanes(vecs):
+        G = 1
+        while G < 64 and G < vecs:
+            G *= 2
+        return G
     vecs = max(1, int(dim) // 4)
-    G = 1
-    while G < 64 and G < vecs:
-        G *= 2
-    slots = 256 // G
+    slots = 256 // pow2_lanes(vecs)
+    slots0 = slots
+    if bf16_grads and int(dim) % 8 == 0 and int(dim) // 8 <= 64:
+        slots0 = 256 // pow2_lanes(int(dim) // 8)
     kps = 6 if bf16_grads else 4
     chunk = slots * kps
-    levels = 1
-    blocks = -(-max(int(n), 1) // chunk)
+    depth = (kps - 1) + (slots0 - 1)
+    blocks = -(-max(int(n), 1) // (slots0 * kps))
     while blocks > 1:
         blocks = -(-(2 * blocks) // chunk)
-        levels += 1
-    return levels * ((kps - 1) + (slots - 1))
+        depth += (kps - 1) + (slots - 1)
+    return depth
 
 
 LONG_BAG = 4096          # a longer bag is pooled in chunks of LONG_CHUNK occurrences
