@@ -325,20 +325,25 @@ __device__ __forceinline__ void slot_prefetched(const Src& S, int64_t q0, int64_
           make_float4(v[4 * a], v[4 * a + 1], v[4 * a + 2], v[4 * a + 3]);
   };
 
-  // (u, bag, row) of position e = r*G + lane in register r
+  // (u, gradient row offset, table row) of position e = r*G + lane in register r: the lane
+  // that loads an entry turns its bag into the offset of the bag's gradient row once, and
+  // the slot's lanes take it by shuffle (rather than each of them dividing by the batch)
   int32_t ekey[kRegs];
-  int32_t ebag[kRegs];
+  int64_t egoff[kRegs];
   int64_t erow[kRegs];
 #pragma unroll
   for (int r = 0; r < kRegs; ++r) {
     const int e = r * G + lane;
     ekey[r] = -1;
-    ebag[r] = 0;
+    egoff[r] = 0;
     erow[r] = -1;
     if (e < KPS && e < len) {
       const int4 sr = S.src[q0 + e];
       ekey[r] = sr.x;
-      ebag[r] = sr.y;
+      uint32_t bag = (uint32_t)sr.y;
+      if ((int64_t)bag >= S.num_bags) bag = 0;
+      const uint32_t t = bag / (uint32_t)S.batch, b = bag - t * (uint32_t)S.batch;
+      egoff[r] = (int64_t)b * S.sb + (int64_t)t * S.st;
       erow[r] = (int64_t)(((uint64_t)(uint32_t)sr.w << 32) | (uint32_t)sr.z);
     }
   }
@@ -350,11 +355,11 @@ __device__ __forceinline__ void slot_prefetched(const Src& S, int64_t q0, int64_
   typename GV::T rv[KPS];
 #pragma unroll
   for (int e = 0; e < KPS; ++e) {
-    kk[e] = __shfl(ekey[e / G], lane0 + (e % G), 64);
-    uint32_t bag = (uint32_t)__shfl(ebag[e / G], lane0 + (e % G), 64);
-    if ((int64_t)bag >= S.num_bags) bag = 0;
-    const uint32_t t = bag / (uint32_t)S.batch, b = bag - t * (uint32_t)S.batch;
-    const int64_t goff = (int64_t)b * S.sb + (int64_t)t * S.st;
+    const int src_lane = lane0 + (e % G);
+    kk[e] = __shfl(ekey[e / G], src_lane, 64);
+    const uint64_t g = egoff[e / G];
+    const int64_t goff = (int64_t)(((uint64_t)(uint32_t)__shfl((int)(uint32_t)(g >> 32), src_lane, 64) << 32) |
+                                   (uint32_t)__shfl((int)(uint32_t)g, src_lane, 64));
     rv[e] = (e < len && col_ok && kk[e] != -1) ? GV::load(S, goff + c) : GV::zero();
   }
 
