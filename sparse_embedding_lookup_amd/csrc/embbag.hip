@@ -304,7 +304,9 @@ __device__ __forceinline__ void pool_block(
       uint4 rv[kU][VPL];
       int bagu[kU];
       int cc = c;
-#pragma unroll
+      // (an explicit count: without it these loops stay rolled for G <= 8, and the row
+      // registers they index go to scratch memory, one load at a time)
+#pragma unroll kU
       for (int u = 0; u < kU; ++u) {
         const int64_t k = k0 + u;
         while (cc < nb - 1 && k >= s_off[cc + 1]) ++cc;
@@ -324,7 +326,7 @@ __device__ __forceinline__ void pool_block(
             rv[u][a] = make_uint4(0u, 0u, 0u, 0u);
         }
       }
-#pragma unroll
+#pragma unroll kU
       for (int u = 0; u < kU; ++u) {
         if (k0 + u >= q1) break;
         if (bagu[u] != c) {                    // the piece of bag c ended at this occurrence
@@ -481,7 +483,7 @@ __global__ __launch_bounds__(kThreads) void long_bag_kernel(
         iv[r] = (e < kU && kk < q1) ? idx[kk] : (TIdx)0;
       }
       uint4 rv[kU][VPL];
-#pragma unroll
+#pragma unroll kU
       for (int u = 0; u < kU; ++u) {
         const int64_t key = base + (int64_t)__shfl(iv[u / G], lane0 + (u % G), 64);
         const bool live = k0 + u < q1;
@@ -497,7 +499,7 @@ __global__ __launch_bounds__(kThreads) void long_bag_kernel(
             rv[u][a] = make_uint4(0u, 0u, 0u, 0u);
         }
       }
-#pragma unroll
+#pragma unroll kU
       for (int u = 0; u < kU; ++u) {
         if (k0 + u >= q1) break;
 #pragma unroll
