@@ -1,11 +1,16 @@
 """Builds libctr.so (HIP for gfx950) in-tree with hipcc.
 
     python -m sparse_embedding_lookup_amd.build
+
+Every kernel must keep its values in registers: the build fails when the compiler's resource
+report gives any kernel scratch memory (a register array it could not keep in registers, or
+spills), which on these kernels has meant loads issued one at a time.
 """
 from __future__ import annotations
 
 import concurrent.futures as cf
 import os
+import re
 import subprocess
 import sys
 
@@ -26,12 +31,30 @@ FLAGS = [
 ]
 
 
+def _scratch_kernels(report: str) -> list:
+    """Kernels with a nonzero ScratchSize in hipcc's kernel-resource-usage remarks."""
+    out, name = [], None
+    for line in report.splitlines():
+        m = re.search(r"remark: Function Name: (\S+)", line)
+        if m:
+            name = m.group(1)
+            continue
+        m = re.search(r"remark:\s+ScratchSize \[bytes/lane\]: (\d+)", line)
+        if m and name and int(m.group(1)) > 0:
+            out.append("%s (%s bytes per lane)" % (name, m.group(1)))
+    return out
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(OBJ, src + ".o")
-    cmd = [HIPCC] + FLAGS + ["-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+    report = ["-Rpass-analysis=kernel-resource-usage"] if src.endswith(".hip") else []
+    cmd = [HIPCC] + FLAGS + report + ["-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("hipcc failed for %s:\n%s\n%s" % (src, " ".join(cmd), r.stderr))
+    scratch = _scratch_kernels(r.stderr)
+    if scratch:
+        raise RuntimeError("kernels of %s use scratch memory:\n  %s" % (src, "\n  ".join(scratch)))
     return obj
 
 
