@@ -8,6 +8,10 @@ the pooling's backward reads bf16 gradient rows and sums them in fp32.
   the two dtypes use different slot depths.  This holds for row gradients only, with the
   nearest-even update, and with stochastic rounding.  For random values the bf16 path
   matches the oracle within rtol * M.
+* Every row width of the first level's lanes (8 columns per lane for widths that are a
+  multiple of 8 up to 512: 1 to 64 lanes per row; 4 columns otherwise), with bf16, fp32 and
+  binary16 tables: integer-valued rows give the fp32 path's bits for the row sums and for the
+  updated table (both roundings), and random rows match the oracle within the tree's bound.
 * A Criteo-shaped step with a bf16 dZ stays within the chained tolerance of the oracle.
   That is test_end_to_end_dlrm_step, since FrontEnd keeps dZ in bf16 when the interaction
   computes in bf16.
@@ -89,3 +93,74 @@ def test_bf16_gradients_sum_like_their_fp32_widening(name):
     want, mag = orc.embbag_bwd(host(gr)[:, 1:, :].astype(np.float64), w.offsets, B, T, inv, U)
     assert_close(host(rr)[:U], want, mag, gamma(segreduce_depth(w.nnz, d, True)),
                  "bf16 row sums")
+
+
+def _synthetic_bags(T, B, rows, seed):
+    """Bags of 0-12 rows over T tables, plus one hot row per table that many bags hold (its
+    segment crosses slots, chunks and carry levels), with the (u, bag, row) quadruples of the
+    sorted occurrences from the oracle's unique."""
+    rng = np.random.default_rng(seed)
+    lens = rng.integers(0, 13, size=(T, B))
+    lens[rng.random((T, B)) < 0.1] = 0
+    idx = []
+    for t in range(T):
+        for b in range(B):
+            r = rng.integers(0, rows[t], size=int(lens[t, b]))
+            if lens[t, b] and rng.random() < 0.6:
+                r[0] = 3                              # the hot row of table t
+            idx.append(r)
+    off = np.zeros(T * B + 1, dtype=np.int64)
+    off[1:] = np.cumsum(lens.reshape(-1))
+    ids = np.concatenate(idx).astype(np.int64)
+    row_base = np.concatenate([[0], np.cumsum(rows)]).astype(np.int64)
+    keys = orc.form_keys(ids, off, T, B, row_base)
+    uniq, inv, perm, _ = orc.unique(keys)
+    n = ids.size
+    bag_of = np.searchsorted(off, np.arange(n), side="right") - 1
+    quads = np.zeros((n, 4), dtype=np.int32)
+    quads[:, 0], quads[:, 1] = inv[perm], bag_of[perm]
+    quads[:, 2:] = uniq[inv[perm]].astype(np.int64).view(np.int32).reshape(-1, 2)
+    return ids, off, uniq, inv, quads
+
+
+# bf16 gradient rows are read 8 columns per lane at the first level when dim is a multiple of
+# 8 up to 512 (1 to 64 lanes per row); other widths take 4 columns per lane
+@pytest.mark.parametrize("dtype,d", [("bf16", 8), ("bf16", 16), ("bf16", 24), ("bf16", 32),
+                                     ("bf16", 40), ("bf16", 64), ("bf16", 96), ("bf16", 200),
+                                     ("bf16", 256), ("bf16", 384), ("bf16", 512),
+                                     ("bf16", 1024), ("f32", 4), ("f32", 12), ("f32", 8),
+                                     ("f16", 48)])
+def test_bf16_gradient_rows_every_width(dtype, d):
+    T, B = 3, 97
+    rows = [700, 300, 900]
+    ids, off, uniq, inv, quads = _synthetic_bags(T, B, rows, d)
+    n, U = ids.size, uniq.size
+    say("bf16 grads width", dtype, d, n, U)
+    rng = np.random.default_rng(d + 11)
+    nu = dev(np.array([U], np.int32))
+    src, offd = dev(quads), dev(off)
+    args = (T * d, d, offd, B, T, d, None, None, nu)
+    # small integers: exact in bf16 and in every fp32 partial sum, so the 8-column lanes
+    # and the fp32 rows' 4-column lanes (other slot depths) give the same bits
+    g16 = dev(rng.integers(-8, 9, size=(B, T, d)).astype(np.float32)).to(torch.bfloat16)
+    g32 = g16.float()
+    r16 = ctr.ctr_embbag_bwd(g16, *args, sorted_src=src, nnz=n)
+    r32 = ctr.ctr_embbag_bwd(g32, *args, sorted_src=src, nnz=n)
+    np.testing.assert_array_equal(host(r16)[:U], host(r32)[:U])
+    uq = dev(uniq)
+    for rounding in (ctr.CTR_ROUND_NEAREST, ctr.CTR_ROUND_STOCHASTIC):
+        if rounding == ctr.CTR_ROUND_STOCHASTIC and dtype == "f32":
+            continue
+        ta, tb = gpu_table(rows, d, dtype, 9), gpu_table(rows, d, dtype, 9)
+        before = ta.clone()
+        for g, t in ((g16, ta), (g32, tb)):
+            ctr.ctr_embbag_bwd_sgd(g, T * d, d, offd, B, T, n, src, nu, t, uq, 0.05,
+                                   rounding=rounding, seed=4321)
+        assert torch.equal(ta, tb), rounding
+        assert not torch.equal(ta, before)
+    # random values against the oracle's sums of the widened values
+    gr = dev(rng.standard_normal((B, T, d)).astype(np.float32)).to(torch.bfloat16)
+    rr = ctr.ctr_embbag_bwd(gr, *args, sorted_src=src, nnz=n)
+    want, mag = orc.embbag_bwd(host(gr).astype(np.float64), off, B, T, inv, U)
+    assert_close(host(rr)[:U], want, mag, gamma(segreduce_depth(n, d, True)),
+                 "bf16 row sums, d=%d" % d)
