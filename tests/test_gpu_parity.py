@@ -328,6 +328,10 @@ INTER_CASES = [
     # fp32 lane kernels at their F / dim boundaries, and shapes left to the LDS kernels
     ("f32", 50, 16, 32), ("f32", 45, 32, 256), ("f32", 19, 17, 48), ("f32", 64, 33, 16),
     ("f32", 3, 8, 8),
+    # matrix-core backward at its 16-row k-step edges (F = 16, 17, 33, 112) and its largest
+    # shape (F = 128: one sample's S fills most of 64 KiB of LDS), narrow and wide rows
+    ("bf16", 21, 16, 32), ("bf16", 23, 17, 64), ("bf16", 30, 33, 128), ("bf16", 17, 112, 64),
+    ("bf16", 7, 128, 128), ("bf16", 11, 128, 16),
 ]
 
 

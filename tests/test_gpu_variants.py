@@ -24,7 +24,7 @@ SELF_CASES = [
     ("f32", 50, 16, 4),            # lanes shape, partials above 64 KiB: LDS-staged fallback
     ("f32", 19, 17, 48), ("f32", 64, 33, 16), ("f32", 45, 32, 256),
     ("bf16", 100, 27, 128), ("bf16", 67, 65, 128), ("bf16", 40, 5, 16), ("bf16", 9, 1, 32),
-    ("bf16", 13, 100, 64),
+    ("bf16", 13, 100, 64), ("bf16", 6, 128, 128), ("bf16", 10, 17, 16),
 ]
 
 
@@ -83,7 +83,7 @@ GRAM_CASES = [
     ("f32", 128, 5, 16), ("f32", 300, 16, 4), ("f32", 77, 1, 8), ("f32", 33, 27, 128),
     ("f32", 19, 17, 48), ("f32", 64, 9, 256),
     ("bf16", 100, 27, 128), ("bf16", 67, 65, 128), ("bf16", 40, 5, 16), ("bf16", 9, 1, 32),
-    ("bf16", 13, 100, 64),
+    ("bf16", 13, 100, 64), ("bf16", 6, 128, 128), ("bf16", 10, 17, 16),
 ]
 
 
