@@ -522,6 +522,8 @@ __device__ __forceinline__ void bwd_write_pairs(__bf16* S, int P, int F, float r
   }
 }
 
+// At most 4 waves per SIMD as the occupancy target: aiming for more, the scheduler keeps
+// registers low by waiting for each Z load before the next (40 loads one at a time).
 template <int KM, int KS, int PS, bool OUTB>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 4)))
 void interaction_bwd_mfma_kernel(
