@@ -486,25 +486,9 @@ __global__ __launch_bounds__(1024) void heads_scan_kernel(uint32_t* __restrict__
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t per = (ntiles + 1023) / 1024;
   const int64_t b0 = (int64_t)threadIdx.x * per;
-  // up to kScanPer counts per thread: every load issued at once (clamped address, value
-  // masked), and kept for the write-back; a loop over longer runs waits load by load
-  constexpr int kScanPer = 32;
-  const bool fast = per <= kScanPer;
-  uint32_t v[kScanPer];
   uint32_t s = 0;
-  if (fast) {
-#pragma unroll
-    for (int j = 0; j < kScanPer; ++j) {
-      const int64_t k = b0 + j;
-      const bool ok = j < per && k < ntiles;
-      const uint32_t x = tile_heads[k < ntiles ? k : ntiles - 1];
-      v[j] = ok ? x : 0u;
-      s += v[j];
-    }
-  } else {
-    for (int64_t j = 0; j < per; ++j)
-      if (b0 + j < ntiles) s += tile_heads[b0 + j];
-  }
+  for (int64_t j = 0; j < per; ++j)
+    if (b0 + j < ntiles) s += tile_heads[b0 + j];
   uint32_t x = s;
   for (int o = 1; o < 64; o <<= 1) {
     const uint32_t y = __shfl_up(x, o, 64);
@@ -518,21 +502,12 @@ __global__ __launch_bounds__(1024) void heads_scan_kernel(uint32_t* __restrict__
     tot += wsum[w];
   }
   uint32_t run = base + x - s;
-  if (fast) {
-#pragma unroll
-    for (int j = 0; j < kScanPer; ++j) {
-      const int64_t k = b0 + j;
-      if (j < per && k < ntiles) tile_heads[k] = run;
-      run += v[j];
+  for (int64_t j = 0; j < per; ++j)
+    if (b0 + j < ntiles) {
+      const uint32_t v = tile_heads[b0 + j];
+      tile_heads[b0 + j] = run;
+      run += v;
     }
-  } else {
-    for (int64_t j = 0; j < per; ++j)
-      if (b0 + j < ntiles) {
-        const uint32_t c = tile_heads[b0 + j];
-        tile_heads[b0 + j] = run;
-        run += c;
-      }
-  }
   if (threadIdx.x == 0) {
     *num_unique = (int32_t)tot;
     if (seg_offsets) seg_offsets[tot] = (int32_t)n;
