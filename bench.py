@@ -353,6 +353,30 @@ def time_dlrm(fe, w, K: int):
     }
 
 
+def interaction_block(w, stage_ms, byts):
+    """The interaction's forward and backward, each alone between HIP events: algorithmic
+    bytes and their fraction of 8 TB/s; with matrix-core compute also the MFMA flops the
+    kernels issue (32x32x16 bf16 tiles: the forward's lower-triangle tiles, d/16 each; the
+    backward's 32-column slabs x 32-row blocks x 16-row k-steps) and their fraction of the
+    2.5 PFLOP/s dense bf16 peak."""
+    B, F, d = w.batch, w.F, w.dim
+    fb, km, ks, nb = (F + 31) // 32, (F + 15) // 16, d // 16, (d + 31) // 32
+    tiles = sum(1 for i in range(fb) for j in range(i + 1) if not (j == i and F - 32 * i < 2))
+    mfma = {"interaction_fwd": tiles * ks, "interaction_bwd": nb * fb * km}
+    out = {}
+    for k in ("interaction_fwd", "interaction_bwd"):
+        ms = stage_ms[k]
+        gbps = byts[k] / (ms * 1e-3) / 1e9
+        e = {"ms": round(ms, 5), "bytes": byts[k], "gbps": gbps, "frac": gbps / HBM_PEAK_GBPS}
+        if w.compute == "bf16":
+            flops = mfma[k] * 32 * 32 * 16 * 2 * B
+            e["mfma_flops"] = flops
+            e["mfma_tflops"] = flops / (ms * 1e-3) / 1e12
+            e["mfma_frac"] = e["mfma_tflops"] / 2500.0
+        out[k] = e
+    return out
+
+
 def measured_traffic(config: str, stage: str):
     """Bytes per launch that the stage's kernel moved between L2 and memory, from the
     committed rocprofv3 counter runs (read requests counted by size, 32/64/128 bytes, and
@@ -942,6 +966,8 @@ def main():
                     / HBM_PEAK_GBPS,
                     "compulsory_frac": compulsory_bytes(w, U, "embbag_fwd")
                     / (stage_ms["embbag_fwd"] * 1e-3) / 1e9 / HBM_PEAK_GBPS},
+        # the interaction alone: memory and matrix-core fractions
+        "interaction": interaction_block(w, stage_ms, byts) if w.interaction else None,
     }
     if not args.no_cpu:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
