@@ -217,6 +217,22 @@ __device__ __forceinline__ void block_range(const SegBlock* blk, int64_t per_blo
   }
 }
 
+// One count per live lane into the wave's bins.  The LDS serves the lanes of one atomic that
+// hit one address one after another, and once a pass has grouped equal keys, a power-law
+// batch's hot row fills most of a wave with one digit: the lanes holding the first live
+// lane's digit are counted by that lane alone, with one add of their number, and only the
+// other lanes add their own one.  Called by every lane of the wave.
+__device__ __forceinline__ void count_digit(uint32_t* bins, uint32_t d, bool live) {
+  const uint64_t act = __ballot(live);
+  if (act == 0ull) return;
+  const int leader = __builtin_ctzll(act);
+  const uint32_t f = (uint32_t)__builtin_amdgcn_readlane((int)d, leader);
+  const bool same = live && d == f;
+  const uint64_t grp = __ballot(same);
+  if ((threadIdx.x & 63) == leader) atomicAdd(&bins[f], (uint32_t)__popcll(grp));
+  else if (live && !same) atomicAdd(&bins[d], 1u);
+}
+
 template <typename K>
 __global__ __launch_bounds__(kThreads) void radix_upsweep_kernel(
     const K* __restrict__ keys, int64_t n, int shift, int nbits, int64_t per_block,
@@ -228,10 +244,11 @@ __global__ __launch_bounds__(kThreads) void radix_upsweep_kernel(
   const uint32_t mask = (1u << nbits) - 1u;
   int64_t beg, end;
   block_range(blk, per_block, n, &beg, &end);
-  // Counting needs no order: LDS atomic adds into the wave's own bins (lanes of one wave
-  // that share a digit are serialised by the LDS; waves never contend).  Keys are read as
-  // 16-byte vectors, kUpU per thread issued before any is counted; the keys before the
-  // first 16-byte boundary of the range and after its last one are read one at a time.
+  // Counting needs no order: LDS atomic adds into the wave's own bins (waves never
+  // contend; count_digit takes the largest group of lanes sharing a digit out of the
+  // serialised adds).  Keys are read as 16-byte vectors, kUpU per thread issued before any
+  // is counted; the keys before the first 16-byte boundary of the range and after its last
+  // one are read one at a time.
   constexpr int V = 16 / (int)sizeof(K);
   const int64_t vbeg = ((beg + V - 1) / V) * V < end ? ((beg + V - 1) / V) * V : end;
   const int64_t vend = vbeg + ((end - vbeg) / V) * V;
@@ -246,12 +263,10 @@ __global__ __launch_bounds__(kThreads) void radix_upsweep_kernel(
     }
 #pragma unroll
     for (int j = 0; j < kUpU; ++j) {
-      const int64_t e = base + ((int64_t)j * kThreads + threadIdx.x) * V;
-      if (e < vend) {
-        const K* kv = reinterpret_cast<const K*>(&raw[j]);
+      const bool live = base + ((int64_t)j * kThreads + threadIdx.x) * V < vend;
+      const K* kv = reinterpret_cast<const K*>(&raw[j]);
 #pragma unroll
-        for (int v = 0; v < V; ++v) atomicAdd(&cnt[wave][(uint32_t)(kv[v] >> shift) & mask], 1u);
-      }
+      for (int v = 0; v < V; ++v) count_digit(cnt[wave], (uint32_t)(kv[v] >> shift) & mask, live);
     }
   }
   for (int64_t e = vend + threadIdx.x; e < end; e += kThreads)

@@ -107,6 +107,10 @@ def _unique_cases():
     cases["raw_small_range_negative"] = (rng.integers(-50, 50, size=10_007), {})
     cases["n1"] = (np.array([123456789], dtype=np.int64), {})
     cases["all_equal"] = (np.full(100_000, 42, dtype=np.int64), dict(modulus=1000))
+    # one row holds 19 of every 20 positions, the rest scattered: after the first pass whole
+    # waves hold one digit with a few others among them
+    hot = np.where(rng.random(300_003) < 0.95, 4093, rng.integers(0, 1 << 20, size=300_003))
+    cases["hot_row_sprinkled"] = (hot.astype(np.int64), dict(modulus=1 << 20))
     cases["all_distinct"] = (rng.permutation(65_536).astype(np.int64), dict(modulus=65_536))
     cases["extremes"] = (np.array([2 ** 63 - 1, -2 ** 63, 0, -1, 1, 2 ** 63 - 1, -2 ** 63],
                                   dtype=np.int64), {})
