@@ -5,7 +5,9 @@
 // "Core Optimizations": collect the batch's IDs, sort them and give each distinct ID a
 // contiguous index.  The sort is ours: reduce-then-scan LSD radix, digits of up to 8 bits
 // spread evenly over the passes (a 28-bit row key takes four 7-bit passes: with 2048-key
-// tiles, wider digits leave too few keys per digit for the output runs to coalesce):
+// tiles, wider digits leave too few keys per digit for the output runs to coalesce), the
+// wider ones last (22 bits: 7, 7, 8), where the earlier passes have already gathered a
+// power-law batch's repeated rows into runs that write out whole:
 //   keys      one wave per 64 bags forms the keys of their occurrences (the bag of each
 //             occurrence comes from a shuffle binary search over the 64 bag ends, so the
 //             table and the bag are known without a search over all offsets)
@@ -772,7 +774,7 @@ void radix_sort(int key_bits, K* keys_a, K* keys_b, uint32_t* vbuf0, uint32_t* v
   int shift = 0;
   for (int p = 0; p < passes; ++p) {
     const int left = key_bits - shift;
-    const int nbits = (left + (passes - p) - 1) / (passes - p);   // spread bits evenly
+    const int nbits = left / (passes - p);   // spread evenly, the wider digits last
     uint32_t* vout = vbuf0 ? vb[(passes - 1 - p) & 1] : nullptr;    // last pass -> vbuf0
     radix_pass<K, ITEMS>(p == 0, kin, vin, bin, kout, vout, bout, n, shift, nbits, per_block,
                          blk, hist, totals, nblocks, s);
