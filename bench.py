@@ -81,10 +81,12 @@ def compulsory_bytes(w, U, stage):
     return U * 4 * d + 4 * n + 8 * (n + 1) + 4 * n * d
 
 
-def stage_bytes(w, U):
+def stage_bytes(w, U, src_bytes=16):
     """Algorithmic bytes moved by each stage (what the method must read and write).  The
     fused backward + SGD counts every occurrence's gradient row (at the gradient's element
-    size), the occurrence's 8-byte index, and the read and write of each updated row."""
+    size), the occurrence's 8-byte index, and the read and write of each updated row.
+    src_bytes: bytes per sorted position of the unique's output for the backward (16 for
+    (u, bag, key) quadruples, 8 for row entries)."""
     n = w.nnz
     d = w.dim
     rb = d * (2 if w.dtype == "bf16" else 4)
@@ -98,8 +100,8 @@ def stage_bytes(w, U):
             # dR and Z read, dZ written at its stored width (bf16 for a bf16 backward)
             "interaction_bwd": 4 * B * (d + P) + (4 + sg) * B * F * d,
             # the pooled step's unique: ids and offsets in; the distinct rows and sorted_src
-            # (16 bytes per position, the backward's input) out
-            "unique": 8 * n + 8 * (nb + 1) + 16 * n + 8 * U,
+            # (the backward's input, src_bytes per position) out
+            "unique": 8 * n + 8 * (nb + 1) + src_bytes * n + 8 * U,
             "embbag_bwd": sg * n * d + 8 * n + 4 * U * d,
             "sparse_sgd": 2 * U * rb + 4 * U * d + 8 * U,
             "embbag_bwd_sgd": sg * n * d + 8 * n + 2 * U * rb,
@@ -791,7 +793,7 @@ def main():
         stage_ms_cold = {n: sum(a.elapsed_time(b) for a, b in cold[n]) / len(cold[n])
                          for n in names}
         del flush, cold
-    byts = stage_bytes(w, U)
+    byts = stage_bytes(w, U, 8 if fe.src_rows else 16)
     # the roofline's kernel: the one that takes the most time per step, among the kernels
     # whose launches the timing marks can bracket (ctr_step_run: the pooling kernel, or the
     # backward's first reduce-by-key level, which carries nearly all of the backward's time)

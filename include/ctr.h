@@ -66,6 +66,14 @@ typedef enum {
  * embeddings); gradients, interaction operands and dZ: CTR_F32 or CTR_BF16. */
 typedef enum { CTR_F32 = 0, CTR_BF16 = 1, CTR_F16 = 2 } ctr_dtype_t;
 typedef enum { CTR_I32 = 0, CTR_I64 = 1 } ctr_index_t;
+/* Layout of sorted_src, one entry per sorted position (ctr_unique_ids writes it, the
+ * backward reads it):
+ *   CTR_SRC_FULL  int32 quadruples (u, bag, key low word, key high word), 16-byte aligned;
+ *   CTR_SRC_ROWS  int32 pairs (key, bag), 8-byte aligned: the key (a table row, below 2^31)
+ *                 stands in for u as the key that groups the positions, so the pair carries
+ *                 half the bytes; for the fused update without row gradients, which needs
+ *                 only the rows. */
+typedef enum { CTR_SRC_FULL = 0, CTR_SRC_ROWS = 1 } ctr_src_layout_t;
 
 /* Library version (major*10000 + minor*100 + patch). */
 int32_t ctr_version(void);
@@ -102,6 +110,9 @@ const char* ctr_last_error_message(void);
  *                    index itself; the key is uniq[u] as int64 (little-endian words).  This
  *                    is the input the backward needs, written by the same pass, so that it
  *                    reaches the gradient row and the table row of a position in one read.
+ *                    With src_layout CTR_SRC_ROWS: sorted_src[2p .. 2p+1] = (key, bag), int32
+ *                    pairs [n] (8-byte aligned), for keys below 2^31 (row_base with
+ *                    total_rows <= 2^31 - 1, or key_modulus <= 2^31; else CTR_ERR_UNSUPPORTED).
  * Key range: with row_base the keys must lie in [0, total_rows); with only a modulus in
  * [0, key_modulus); otherwise any int64.  The sort covers only the live key bits.
  * max_table_rows (0: unknown): the row count of the largest table.  With row_base and no
@@ -116,7 +127,8 @@ int32_t ctr_unique_ids(const void* ids, int32_t id_type, int64_t n,
                        int64_t key_modulus,
                        int64_t* uniq, int32_t* inverse, int32_t* num_unique,
                        int32_t* perm, int32_t* seg_offsets, int32_t* sorted_src,
-                       void* workspace, size_t* workspace_bytes, void* stream);
+                       int32_t src_layout, void* workspace, size_t* workspace_bytes,
+                       void* stream);
 
 /*
  * ctr_gather_rows -- [TN] "Core Optimizations": fetch the batch's rows into the
@@ -175,7 +187,10 @@ int32_t ctr_embbag_bwd(const float* grad, int64_t grad_stride_b, int64_t grad_st
  * with exactly the arithmetic of ctr_sparse_sgd with the same rounding and seed (so the table
  * ends bit-identical to the two-call path), without writing g to memory and reading it back.
  * Grouping and table rows come from ctr_unique_ids' sorted_src (u, bag, key); uniq serves the
- * rows of segments that span several chunks.
+ * rows of segments that span several chunks.  With src_layout CTR_SRC_ROWS the entries are
+ * (row, bag) pairs: the rows key the segments and address the table, uniq is not read (may
+ * be NULL), a table is required, row_grads must be NULL (there is no u to index it), and
+ * total_rows must be below 2^31.  The table ends bit-identical to the CTR_SRC_FULL call.
  *   grad: grad_dtype elements, CTR_F32 or CTR_BF16 (widened exactly; the sums stay fp32),
  *         8-byte aligned for bf16, 16-byte for fp32; strides in elements as in ctr_embbag_bwd.
  *   table: dtype/total_rows/dim as in ctr_sparse_sgd (dim <= 1024), or NULL: then only
@@ -187,10 +202,10 @@ int32_t ctr_embbag_bwd(const float* grad, int64_t grad_stride_b, int64_t grad_st
 int32_t ctr_embbag_bwd_sgd(const void* grad, int32_t grad_dtype, int64_t grad_stride_b,
                            int64_t grad_stride_t, const int64_t* offsets, int64_t batch,
                            int32_t num_tables, int64_t nnz, const int32_t* sorted_src,
-                           const int32_t* num_unique, void* table, int32_t dtype,
-                           int64_t total_rows, int32_t dim, const int64_t* uniq, float lr,
-                           int32_t rounding, uint64_t seed, float* row_grads, void* workspace,
-                           size_t* workspace_bytes, void* stream);
+                           int32_t src_layout, const int32_t* num_unique, void* table,
+                           int32_t dtype, int64_t total_rows, int32_t dim, const int64_t* uniq,
+                           float lr, int32_t rounding, uint64_t seed, float* row_grads,
+                           void* workspace, size_t* workspace_bytes, void* stream);
 
 /*
  * ctr_embbag_bwd_sgd_noalloc -- ctr_embbag_bwd_sgd without a workspace, for callers that
@@ -208,10 +223,10 @@ int32_t ctr_embbag_bwd_sgd(const void* grad, int32_t grad_dtype, int64_t grad_st
 int32_t ctr_embbag_bwd_sgd_noalloc(const void* grad, int32_t grad_dtype, int64_t grad_stride_b,
                                    int64_t grad_stride_t, const int64_t* offsets, int64_t batch,
                                    int32_t num_tables, int64_t nnz, const int32_t* sorted_src,
-                                   const int32_t* num_unique, void* table, int32_t dtype,
-                                   int64_t total_rows, int32_t dim, const int64_t* uniq, float lr,
-                                   int32_t rounding, uint64_t seed, float* row_grads,
-                                   void* stream);
+                                   int32_t src_layout, const int32_t* num_unique, void* table,
+                                   int32_t dtype, int64_t total_rows, int32_t dim,
+                                   const int64_t* uniq, float lr, int32_t rounding,
+                                   uint64_t seed, float* row_grads, void* stream);
 /* Scratch bytes ctr_embbag_bwd_sgd_noalloc needs for nnz occurrences of dim-wide rows
  * ((size_t)-1 for a bad size), and the capacity it has. */
 size_t ctr_embbag_bwd_noalloc_scratch_bytes(int64_t nnz, int32_t dim);
@@ -438,7 +453,8 @@ int32_t ctr_validate_csr(const void* indices, int32_t index_type, int64_t nnz,
  * Unique outputs exist in CTR_STEP_SETS = 3 sets: the serial schedule uses set 0, the
  * pipelined schedules of ctr_step_run sets 0 and 1, ctr_step_run_deep all three (an unused
  * set may repeat set 0).  Each array has capacity nnz
- * (seg_offsets nnz + 1; sorted_src 4 int32 per position, 16-byte aligned).  Workspaces are
+ * (seg_offsets nnz + 1; sorted_src 4 int32 per position, 16-byte aligned, or 2 int32,
+ * 8-byte aligned, with src_layout CTR_SRC_ROWS).  Workspaces are
  * sized by the two-call queries of ctr_unique_ids and ctr_embbag_bwd.  row_grads
  * (fp32 [nnz, dim]) is optional.
  */
@@ -503,6 +519,8 @@ typedef struct {
                                      ctr_unique_ids) */
   void* ws_pool;                  /* the pooling's workspace (ctr_embbag_fwd's query) */
   size_t ws_pool_bytes;
+  int32_t src_layout;             /* sorted_src's layout, CTR_SRC_FULL or CTR_SRC_ROWS (the
+                                     latter needs row_grads NULL) */
 } ctr_step_t;
 
 /*

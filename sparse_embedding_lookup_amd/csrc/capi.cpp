@@ -26,6 +26,8 @@ int32_t hip_status(hipError_t e, const char* where) {
 }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+// Alignment mask of sorted_src: 16-byte quadruples, or 8-byte row entries.
+uintptr_t src_align(int32_t layout) { return layout == CTR_SRC_ROWS ? 7u : 15u; }
 
 constexpr int64_t kMaxElems = 2147483647;  // int32 positions and indices
 
@@ -104,10 +106,18 @@ int32_t ctr_unique_ids(const void* ids, int32_t id_type, int64_t n, const int64_
                        int64_t total_rows, int64_t max_table_rows, int64_t key_modulus,
                        int64_t* uniq,
                        int32_t* inverse, int32_t* num_unique, int32_t* perm,
-                       int32_t* seg_offsets, int32_t* sorted_src, void* workspace,
-                       size_t* workspace_bytes, void* stream) {
+                       int32_t* seg_offsets, int32_t* sorted_src, int32_t src_layout,
+                       void* workspace, size_t* workspace_bytes, void* stream) {
   g_msg[0] = 0;
   if (!workspace_bytes) return fail(CTR_ERR_INVALID_ARGUMENT, "workspace_bytes is NULL");
+  if (src_layout != CTR_SRC_FULL && src_layout != CTR_SRC_ROWS)
+    return fail(CTR_ERR_INVALID_ARGUMENT, "src_layout %d is not CTR_SRC_FULL or CTR_SRC_ROWS",
+                src_layout);
+  // row entries hold the key in 32 bits: keys below 2^31 (table rows, or a modulus)
+  if (src_layout == CTR_SRC_ROWS && !(row_base ? total_rows <= kMaxElems
+                                               : (key_modulus > 0 && key_modulus <= kMaxElems + 1)))
+    return fail(CTR_ERR_UNSUPPORTED,
+                "CTR_SRC_ROWS needs keys below 2^31 (total_rows with row_base, or key_modulus)");
   if (n < 0 || n > kMaxElems) return fail(CTR_ERR_INVALID_ARGUMENT, "n=%lld out of [0, 2^31)", (long long)n);
   if (id_type != CTR_I32 && id_type != CTR_I64)
     return fail(CTR_ERR_INVALID_ARGUMENT, "id_type %d is not CTR_I32 or CTR_I64", id_type);
@@ -132,8 +142,9 @@ int32_t ctr_unique_ids(const void* ids, int32_t id_type, int64_t n, const int64_
   if (!num_unique) return fail(CTR_ERR_INVALID_ARGUMENT, "num_unique is NULL");
   if (n > 0 && (!ids || !uniq))
     return fail(CTR_ERR_INVALID_ARGUMENT, "ids and uniq are required");
-  if (sorted_src && (reinterpret_cast<uintptr_t>(sorted_src) & 15u))
-    return fail(CTR_ERR_UNSUPPORTED, "sorted_src is not 16-byte aligned");
+  if (sorted_src && (reinterpret_cast<uintptr_t>(sorted_src) & src_align(src_layout)))
+    return fail(CTR_ERR_UNSUPPORTED, "sorted_src is not %d-byte aligned",
+                (int)src_align(src_layout) + 1);
   int bits;
   bool is_signed = false;
   if (row_base) {
@@ -157,8 +168,8 @@ int32_t ctr_unique_ids(const void* ids, int32_t id_type, int64_t n, const int64_
   return hip_status(ctr::launch_unique(ids, id_type == CTR_I64, n, offsets, batch, num_tables,
                                        row_base, key_modulus, bits, seg_bits, is_signed, uniq,
                                        inverse,
-                                       num_unique, perm, seg_offsets,
-                                       reinterpret_cast<int4*>(sorted_src), workspace,
+                                       num_unique, perm, seg_offsets, sorted_src,
+                                       src_layout == CTR_SRC_ROWS, workspace,
                                        (hipStream_t)stream),
                     "ctr_unique_ids");
 }
@@ -256,16 +267,16 @@ int32_t ctr_embbag_bwd(const float* grad, int64_t grad_stride_b, int64_t grad_st
   if (!aligned16(workspace)) return fail(CTR_ERR_UNSUPPORTED, "workspace is not 16-byte aligned");
   return hip_status(ctr::launch_embbag_bwd(grad, false, grad_stride_b, grad_stride_t, offsets,
                                            batch, num_tables, dim, nnz, perm, inverse,
-                                           reinterpret_cast<const int4*>(sorted_src), num_unique,
-                                           row_grads, nullptr, 0, 0, nullptr, 0.f, 0, workspace,
-                                           (hipStream_t)stream),
+                                           sorted_src, false, num_unique, row_grads, nullptr, 0,
+                                           0, nullptr, 0.f, 0, workspace, (hipStream_t)stream),
                     "ctr_embbag_bwd");
 }
 
 static int32_t embbag_bwd_sgd_common(const void* grad, bool grad_bf16, int64_t grad_stride_b,
                                      int64_t grad_stride_t, const int64_t* offsets,
                                      int64_t batch, int32_t num_tables, int64_t nnz,
-                                     const int32_t* sorted_src, const int32_t* num_unique,
+                                     const int32_t* sorted_src, int32_t src_layout,
+                                     const int32_t* num_unique,
                                      void* table, int32_t dtype, int64_t total_rows, int32_t dim,
                                      const int64_t* uniq, float lr, float* row_grads,
                                      void* workspace, size_t* workspace_bytes, bool stochastic,
@@ -309,7 +320,13 @@ static int32_t embbag_bwd_sgd_common(const void* grad, bool grad_bf16, int64_t g
                   need);
   }
   if (!offsets || !num_unique) return fail(CTR_ERR_INVALID_ARGUMENT, "offsets and num_unique are required");
-  if (nnz > 0 && (!grad || !sorted_src || (table && !uniq)))
+  const bool rows = src_layout == CTR_SRC_ROWS;
+  if (rows && (!table || row_grads))
+    return fail(CTR_ERR_INVALID_ARGUMENT,
+                "CTR_SRC_ROWS entries need a table and no row_grads (they carry no u)");
+  if (rows && total_rows > kMaxElems)
+    return fail(CTR_ERR_UNSUPPORTED, "CTR_SRC_ROWS needs total_rows below 2^31");
+  if (nnz > 0 && (!grad || !sorted_src || (table && !rows && !uniq)))
     return fail(CTR_ERR_INVALID_ARGUMENT, "grad, sorted_src and uniq are required");
   if (!table && !row_grads)
     return fail(CTR_ERR_INVALID_ARGUMENT, "without a table, row_grads is required");
@@ -323,8 +340,9 @@ static int32_t embbag_bwd_sgd_common(const void* grad, bool grad_bf16, int64_t g
     return fail(CTR_ERR_UNSUPPORTED,
                 "grad must be %d-byte aligned, row_grads 16-byte, strides multiple of 4",
                 grad_bf16 ? 8 : 16);
-  if (reinterpret_cast<uintptr_t>(sorted_src) & 15u)
-    return fail(CTR_ERR_UNSUPPORTED, "sorted_src is not 16-byte aligned");
+  if (reinterpret_cast<uintptr_t>(sorted_src) & src_align(src_layout))
+    return fail(CTR_ERR_UNSUPPORTED, "sorted_src is not %d-byte aligned",
+                (int)src_align(src_layout) + 1);
   if (!noalloc && !aligned16(workspace))
     return fail(CTR_ERR_UNSUPPORTED, "workspace is not 16-byte aligned");
   const int mode = !table               ? 0
@@ -334,13 +352,12 @@ static int32_t embbag_bwd_sgd_common(const void* grad, bool grad_bf16, int64_t g
   if (noalloc)
     return hip_status(ctr::launch_embbag_bwd_noalloc(
                           grad, grad_bf16, grad_stride_b, grad_stride_t, offsets, batch,
-                          num_tables, dim, nnz, reinterpret_cast<const int4*>(sorted_src),
-                          row_grads, table, mode, total_rows, uniq, lr, seed,
-                          (hipStream_t)stream),
+                          num_tables, dim, nnz, sorted_src, rows, row_grads, table, mode,
+                          total_rows, uniq, lr, seed, (hipStream_t)stream),
                       name);
   return hip_status(ctr::launch_embbag_bwd(grad, grad_bf16, grad_stride_b, grad_stride_t,
                                            offsets, batch, num_tables, dim, nnz, nullptr,
-                                           nullptr, reinterpret_cast<const int4*>(sorted_src),
+                                           nullptr, sorted_src, rows,
                                            num_unique, row_grads, table, mode, total_rows, uniq,
                                            lr, seed, workspace, (hipStream_t)stream, l0_begin,
                                            l0_end),
@@ -351,12 +368,12 @@ static int32_t embbag_bwd_sgd_common(const void* grad, bool grad_bf16, int64_t g
 static int32_t embbag_bwd_sgd_coded(const void* grad, int32_t grad_dtype, int64_t grad_stride_b,
                                     int64_t grad_stride_t, const int64_t* offsets, int64_t batch,
                                     int32_t num_tables, int64_t nnz, const int32_t* sorted_src,
-                                    const int32_t* num_unique, void* table, int32_t dtype,
-                                    int64_t total_rows, int32_t dim, const int64_t* uniq,
-                                    float lr, int32_t rounding, uint64_t seed, float* row_grads,
-                                    void* workspace, size_t* workspace_bytes, void* stream,
-                                    const char* name, void* l0_begin, void* l0_end,
-                                    bool noalloc) {
+                                    int32_t src_layout, const int32_t* num_unique, void* table,
+                                    int32_t dtype, int64_t total_rows, int32_t dim,
+                                    const int64_t* uniq, float lr, int32_t rounding,
+                                    uint64_t seed, float* row_grads, void* workspace,
+                                    size_t* workspace_bytes, void* stream, const char* name,
+                                    void* l0_begin, void* l0_end, bool noalloc) {
   if (grad_dtype != CTR_F32 && grad_dtype != CTR_BF16) {
     g_msg[0] = 0;
     return fail(CTR_ERR_INVALID_ARGUMENT, "grad_dtype %d is not CTR_F32 or CTR_BF16", grad_dtype);
@@ -365,8 +382,14 @@ static int32_t embbag_bwd_sgd_coded(const void* grad, int32_t grad_dtype, int64_
     g_msg[0] = 0;
     return fail(CTR_ERR_INVALID_ARGUMENT, "unknown rounding %d", rounding);
   }
+  if (src_layout != CTR_SRC_FULL && src_layout != CTR_SRC_ROWS) {
+    g_msg[0] = 0;
+    return fail(CTR_ERR_INVALID_ARGUMENT, "src_layout %d is not CTR_SRC_FULL or CTR_SRC_ROWS",
+                src_layout);
+  }
   return embbag_bwd_sgd_common(grad, grad_dtype == CTR_BF16, grad_stride_b, grad_stride_t,
-                               offsets, batch, num_tables, nnz, sorted_src, num_unique, table,
+                               offsets, batch, num_tables, nnz, sorted_src, src_layout,
+                               num_unique, table,
                                dtype, total_rows, dim, uniq, lr, row_grads, workspace,
                                workspace_bytes, rounding == CTR_ROUND_STOCHASTIC, seed, stream,
                                name, l0_begin, l0_end, noalloc);
@@ -380,13 +403,14 @@ namespace ctr {
 int32_t embbag_bwd_sgd_marked(const void* grad, int32_t grad_dtype, int64_t grad_stride_b,
                               int64_t grad_stride_t, const int64_t* offsets, int64_t batch,
                               int32_t num_tables, int64_t nnz, const int32_t* sorted_src,
-                              const int32_t* num_unique, void* table, int32_t dtype,
-                              int64_t total_rows, int32_t dim, const int64_t* uniq, float lr,
-                              int32_t rounding, uint64_t seed, float* row_grads, void* workspace,
-                              size_t* workspace_bytes, void* stream, void* l0_begin,
-                              void* l0_end) {
+                              int32_t src_layout, const int32_t* num_unique, void* table,
+                              int32_t dtype, int64_t total_rows, int32_t dim,
+                              const int64_t* uniq, float lr, int32_t rounding, uint64_t seed,
+                              float* row_grads, void* workspace, size_t* workspace_bytes,
+                              void* stream, void* l0_begin, void* l0_end) {
   return embbag_bwd_sgd_coded(grad, grad_dtype, grad_stride_b, grad_stride_t, offsets, batch,
-                              num_tables, nnz, sorted_src, num_unique, table, dtype, total_rows,
+                              num_tables, nnz, sorted_src, src_layout, num_unique, table, dtype,
+                              total_rows,
                               dim, uniq, lr, rounding, seed, row_grads, workspace,
                               workspace_bytes, stream, "ctr_step_run (backward)", l0_begin,
                               l0_end, false);
@@ -398,12 +422,13 @@ extern "C" {
 int32_t ctr_embbag_bwd_sgd(const void* grad, int32_t grad_dtype, int64_t grad_stride_b,
                            int64_t grad_stride_t, const int64_t* offsets, int64_t batch,
                            int32_t num_tables, int64_t nnz, const int32_t* sorted_src,
-                           const int32_t* num_unique, void* table, int32_t dtype,
-                           int64_t total_rows, int32_t dim, const int64_t* uniq, float lr,
-                           int32_t rounding, uint64_t seed, float* row_grads, void* workspace,
-                           size_t* workspace_bytes, void* stream) {
+                           int32_t src_layout, const int32_t* num_unique, void* table,
+                           int32_t dtype, int64_t total_rows, int32_t dim, const int64_t* uniq,
+                           float lr, int32_t rounding, uint64_t seed, float* row_grads,
+                           void* workspace, size_t* workspace_bytes, void* stream) {
   return embbag_bwd_sgd_coded(grad, grad_dtype, grad_stride_b, grad_stride_t, offsets, batch,
-                              num_tables, nnz, sorted_src, num_unique, table, dtype, total_rows,
+                              num_tables, nnz, sorted_src, src_layout, num_unique, table, dtype,
+                              total_rows,
                               dim, uniq, lr, rounding, seed, row_grads, workspace,
                               workspace_bytes, stream, "ctr_embbag_bwd_sgd", nullptr, nullptr,
                               false);
@@ -412,12 +437,13 @@ int32_t ctr_embbag_bwd_sgd(const void* grad, int32_t grad_dtype, int64_t grad_st
 int32_t ctr_embbag_bwd_sgd_noalloc(const void* grad, int32_t grad_dtype, int64_t grad_stride_b,
                                    int64_t grad_stride_t, const int64_t* offsets, int64_t batch,
                                    int32_t num_tables, int64_t nnz, const int32_t* sorted_src,
-                                   const int32_t* num_unique, void* table, int32_t dtype,
-                                   int64_t total_rows, int32_t dim, const int64_t* uniq, float lr,
-                                   int32_t rounding, uint64_t seed, float* row_grads,
-                                   void* stream) {
+                                   int32_t src_layout, const int32_t* num_unique, void* table,
+                                   int32_t dtype, int64_t total_rows, int32_t dim,
+                                   const int64_t* uniq, float lr, int32_t rounding,
+                                   uint64_t seed, float* row_grads, void* stream) {
   return embbag_bwd_sgd_coded(grad, grad_dtype, grad_stride_b, grad_stride_t, offsets, batch,
-                              num_tables, nnz, sorted_src, num_unique, table, dtype, total_rows,
+                              num_tables, nnz, sorted_src, src_layout, num_unique, table, dtype,
+                              total_rows,
                               dim, uniq, lr, rounding, seed, row_grads, nullptr, nullptr, stream,
                               "ctr_embbag_bwd_sgd_noalloc", nullptr, nullptr, true);
 }

@@ -14,13 +14,14 @@ namespace ctr {
 // unique.hip
 size_t unique_workspace_bytes(int64_t n);
 // seg_bits > 0: the table-segmented sort over seg_bits local row bits (row_base and offsets
-// given, (num_tables - 1) << seg_bits below 2^32, at most 512 tables).
+// given, (num_tables - 1) << seg_bits below 2^32, at most 512 tables).  sorted_src: int4
+// (u, bag, key words) per sorted position, or with src_rows int2 (key, bag) (keys below 2^31).
 hipError_t launch_unique(const void* ids, bool ids64, int64_t n, const int64_t* offsets,
                          int64_t batch, int32_t num_tables, const int64_t* row_base,
                          int64_t modulus, int key_bits, int seg_bits, bool key_signed,
                          int64_t* uniq, int32_t* inverse, int32_t* num_unique, int32_t* perm,
-                         int32_t* seg_offsets, int4* sorted_src, void* workspace,
-                         hipStream_t s);
+                         int32_t* seg_offsets, void* sorted_src, bool src_rows,
+                         void* workspace, hipStream_t s);
 
 // embbag.hip (elt: the table's kElt code, ctr_internal.h)
 // The pooling; workspace (embbag_fwd_workspace_bytes) holds the long bags' chunk partials.
@@ -45,11 +46,14 @@ hipError_t launch_validate_csr(const void* idx, bool idx64, int64_t nnz, const i
 
 // segreduce.hip
 size_t embbag_bwd_workspace_bytes(int64_t nnz, int dim);
+// sorted_src: int4 (u, bag, row words), or with src_rows int2 (row, bag): then a table and
+// no row_grads.
 hipError_t launch_embbag_bwd(const void* grad, bool grad_bf16, int64_t sb, int64_t st,
                              const int64_t* offsets,
                              int64_t batch, int32_t num_tables, int dim, int64_t nnz,
-                             const int32_t* perm, const int32_t* inverse, const int4* sorted_src,
-                             const int32_t* num_unique, float* row_grads, void* table,
+                             const int32_t* perm, const int32_t* inverse, const void* sorted_src,
+                             bool src_rows, const int32_t* num_unique, float* row_grads,
+                             void* table,
                              int sgd_mode, int64_t total_rows, const int64_t* uniq, float lr,
                              uint64_t seed, void* workspace, hipStream_t s,
                              void* l0_begin = nullptr, void* l0_end = nullptr);
@@ -60,8 +64,8 @@ constexpr size_t kNoallocScratchBytes = size_t(64) << 20;
 size_t embbag_bwd_noalloc_bytes(int64_t nnz, int dim);
 hipError_t launch_embbag_bwd_noalloc(const void* grad, bool grad_bf16, int64_t sb, int64_t st,
                                      const int64_t* offsets, int64_t batch, int32_t num_tables,
-                                     int dim, int64_t nnz, const int4* sorted_src,
-                                     float* row_grads, void* table, int sgd_mode,
+                                     int dim, int64_t nnz, const void* sorted_src,
+                                     bool src_rows, float* row_grads, void* table, int sgd_mode,
                                      int64_t total_rows, const int64_t* uniq, float lr,
                                      uint64_t seed, hipStream_t s);
 // The fused backward + SGD entry (ctr_embbag_bwd_sgd) with timing marks around its first
@@ -69,11 +73,11 @@ hipError_t launch_embbag_bwd_noalloc(const void* grad, bool grad_bf16, int64_t s
 int32_t embbag_bwd_sgd_marked(const void* grad, int32_t grad_dtype, int64_t grad_stride_b,
                               int64_t grad_stride_t, const int64_t* offsets, int64_t batch,
                               int32_t num_tables, int64_t nnz, const int32_t* sorted_src,
-                              const int32_t* num_unique, void* table, int32_t dtype,
-                              int64_t total_rows, int32_t dim, const int64_t* uniq, float lr,
-                              int32_t rounding, uint64_t seed, float* row_grads, void* workspace,
-                              size_t* workspace_bytes, void* stream, void* l0_begin,
-                              void* l0_end);
+                              int32_t src_layout, const int32_t* num_unique, void* table,
+                              int32_t dtype, int64_t total_rows, int32_t dim,
+                              const int64_t* uniq, float lr, int32_t rounding, uint64_t seed,
+                              float* row_grads, void* workspace, size_t* workspace_bytes,
+                              void* stream, void* l0_begin, void* l0_end);
 
 // dict.hip
 hipError_t launch_dict_build(const int64_t* keys, const int32_t* rows, const int32_t* hot_slots,

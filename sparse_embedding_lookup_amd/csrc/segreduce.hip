@@ -2,7 +2,8 @@
 // the batch's distinct rows ("How TensorNet Supercharges Sparse Feature Training on
 // TensorFlow", "Synchronous Architecture": only rows present in the batch get anything).
 //
-// Input: the unique step's (u, bag, table row) per sorted position, or perm (sorted
+// Input: the unique step's (u, bag, table row) per sorted position, or its (table row, bag)
+// when the update needs no row gradients (the row then keys the segments), or perm (sorted
 // position -> occurrence) and inverse (occurrence -> u), from which two small kernels build
 // (u, bag) per sorted position first (a wave expands 64 bags by a shuffle binary search
 // over their ends; then one gather in sorted order).  Then a deterministic reduce-by-key
@@ -74,15 +75,35 @@ __global__ __launch_bounds__(kThreads) void seg_src_kernel(const int32_t* __rest
   src[p] = r;
 }
 
-// Level-0 entries: the sorted (u, bag, key) quadruples, and the per-bag gradient rows they
-// point at, fp32 or bf16 (GB; widened exactly).  Offsets are in elements.
-template <bool GB>
+// Level-0 entries, one per sorted position, and the per-bag gradient rows they point at, fp32
+// or bf16 (GB; widened exactly).  Offsets are in elements.  An entry is 16 bytes, (u, bag,
+// table row as two words), or with ROWS 8 bytes, (table row, bag): the row then stands in for
+// the distinct-row index u as the key that groups the positions (the two are in one-to-one
+// order-preserving correspondence), which is all the fused update needs.
+template <bool GB, bool ROWS>
 struct L0SourceT {
   static constexpr bool kBf16 = GB;
-  const int4* src;
+  static constexpr bool kRows = ROWS;
+  const void* src;
   const void* grad;
   int64_t sb, st, batch, num_bags;
-  __device__ __forceinline__ int32_t key(int64_t p) const { return src[p].x; }
+  struct Entry {
+    int32_t key, bag;
+    int64_t row;
+  };
+  __device__ __forceinline__ Entry entry(int64_t p) const {
+    if constexpr (ROWS) {
+      const int2 e = static_cast<const int2*>(src)[p];
+      return Entry{e.x, e.y, (int64_t)e.x};
+    } else {
+      const int4 e = static_cast<const int4*>(src)[p];
+      return Entry{e.x, e.y, (int64_t)(((uint64_t)(uint32_t)e.w << 32) | (uint32_t)e.z)};
+    }
+  }
+  __device__ __forceinline__ int32_t key(int64_t p) const {
+    if constexpr (ROWS) return static_cast<const int2*>(src)[p].x;
+    else return static_cast<const int4*>(src)[p].x;
+  }
   // Four consecutive gradient values at element offset `off` (a multiple of 4), loaded raw
   // (8 bytes of bf16, or 16 of fp32) and widened only where they are added, so that a
   // slot's loads issue together and bf16 rows stay packed in registers until then.
@@ -104,8 +125,8 @@ struct L0SourceT {
       return r;
   }
 };
-using L0Source = L0SourceT<false>;
-using L0SourceB = L0SourceT<true>;
+using L0Source = L0SourceT<false, false>;
+using L0SourceB = L0SourceT<true, false>;
 
 struct LnSource {
   static constexpr bool kBf16 = false;
@@ -151,7 +172,7 @@ struct SgdTarget {
   char* table;
   int64_t total_rows;
   int64_t row_bytes;
-  const int64_t* uniq;
+  const int64_t* uniq;     // the table row of each u; null when the keys are the rows
   float lr;
   uint64_t seed;
 };
@@ -338,13 +359,13 @@ __device__ __forceinline__ void slot_prefetched(const Src& S, int64_t q0, int64_
     egoff[r] = 0;
     erow[r] = -1;
     if (e < KPS && e < len) {
-      const int4 sr = S.src[q0 + e];
-      ekey[r] = sr.x;
-      uint32_t bag = (uint32_t)sr.y;
+      const auto en = S.entry(q0 + e);
+      ekey[r] = en.key;
+      uint32_t bag = (uint32_t)en.bag;
       if ((int64_t)bag >= S.num_bags) bag = 0;
       const uint32_t t = bag / (uint32_t)S.batch, b = bag - t * (uint32_t)S.batch;
       egoff[r] = (int64_t)b * S.sb + (int64_t)t * S.st;
-      erow[r] = (int64_t)(((uint64_t)(uint32_t)sr.w << 32) | (uint32_t)sr.z);
+      erow[r] = en.row;
     }
   }
   const int32_t kb = key_before<true>(S, q0);
@@ -475,7 +496,7 @@ __device__ __forceinline__ void reduce_chunk(
     if (u < 0 || (int64_t)u >= capacity) return;
     if (row_grads) write_row(row_grads + (int64_t)u * dim, r);
     if constexpr (MODE != 0) {
-      const int64_t key = sgd.uniq[u];
+      const int64_t key = sgd.uniq ? sgd.uniq[u] : (int64_t)u;   // no uniq: keys are rows
       if (key < 0 || key >= sgd.total_rows) return;
       char* wrow = sgd.table + key * sgd.row_bytes;
 #pragma unroll
@@ -519,9 +540,9 @@ __device__ __forceinline__ void reduce_chunk(
       ebag[r] = 0;
       if (e < KPS && p < q1) {
         if constexpr (L0) {
-          const int4 sr = S.src[p];
-          ekey[r] = sr.x;
-          ebag[r] = sr.y;
+          const auto en = S.entry(p);
+          ekey[r] = en.key;
+          ebag[r] = en.bag;
         } else {
           ekey[r] = S.keys[p];
         }
@@ -859,10 +880,12 @@ size_t embbag_bwd_noalloc_bytes(int64_t nnz, int dim) {
     }                                                                       \
   } while (0)
 
+// capacity: keys are below it (the distinct rows' count bound nnz, or the table's rows when
+// the keys are rows).
 template <int MODE, typename L0S>
-static hipError_t segreduce_levels(const L0S& s0, int64_t nnz, int dim, float* row_grads,
-                                   const SgdTarget& sgd, BwdWs& w, hipStream_t s, void* l0_begin,
-                                   void* l0_end) {
+static hipError_t segreduce_levels(const L0S& s0, int64_t nnz, int64_t capacity, int dim,
+                                   float* row_grads, const SgdTarget& sgd, BwdWs& w,
+                                   hipStream_t s, void* l0_begin, void* l0_end) {
   hipError_t e = record_mark(l0_begin, s);
   if (e != hipSuccess) return e;
   const RowGeom rg = row_geom(dim / 4);
@@ -878,16 +901,16 @@ static hipError_t segreduce_levels(const L0S& s0, int64_t nnz, int dim, float* r
       CTR_SEG_DISPATCH(g8, 1, {
         (void)VPL;
         segreduce_kernel<true, true, G, 2, MODE, KPS, L0S><<<(unsigned)blocks, kThreads, 0, s>>>(
-            s0, nnz, dim, nnz, row_grads, sgd, blocks > 1 ? w.ckeys[cur] : nullptr, w.crows[cur],
-            w.ticket, nullptr);
+            s0, nnz, dim, capacity, row_grads, sgd, blocks > 1 ? w.ckeys[cur] : nullptr,
+            w.crows[cur], w.ticket, nullptr);
       });
     }
   }
   if (!g8) {
     CTR_SEG_DISPATCH(rg.G, rg.VPL, {
       segreduce_kernel<true, false, G, VPL, MODE, KPS, L0S><<<(unsigned)blocks, kThreads, 0, s>>>(
-          s0, nnz, dim, nnz, row_grads, sgd, blocks > 1 ? w.ckeys[cur] : nullptr, w.crows[cur],
-          w.ticket, nullptr);
+          s0, nnz, dim, capacity, row_grads, sgd, blocks > 1 ? w.ckeys[cur] : nullptr,
+          w.crows[cur], w.ticket, nullptr);
     });
   }
   e = record_mark(l0_end, s);
@@ -900,7 +923,7 @@ static hipError_t segreduce_levels(const L0S& s0, int64_t nnz, int dim, float* r
       // a level whose carries fit one chunk finishes the tree itself
       const bool fold = blocks > 1 && 2 * blocks <= chunk && blocks <= kFoldBlocks;
       segreduce_kernel<false, false, G, VPL, MODE, KPS, LnSource><<<(unsigned)blocks, kThreads, 0, s>>>(
-          sn, len, dim, nnz, row_grads, sgd, blocks > 1 ? w.ckeys[cur ^ 1] : nullptr,
+          sn, len, dim, capacity, row_grads, sgd, blocks > 1 ? w.ckeys[cur ^ 1] : nullptr,
           w.crows[cur ^ 1], fold ? w.ticket : nullptr, w.crows[cur]);
       cur ^= 1;
       if (fold) break;
@@ -914,14 +937,14 @@ namespace {
 hipError_t embbag_bwd_levels(const BwdWs& w, const void* grad, bool grad_bf16, int64_t sb,
                              int64_t st, const int64_t* offsets, int64_t batch,
                              int32_t num_tables, int dim, int64_t nnz, const int32_t* perm,
-                             const int32_t* inverse, const int4* sorted_src, float* row_grads,
-                             void* table, int sgd_mode, int64_t total_rows, const int64_t* uniq,
-                             float lr, uint64_t seed, hipStream_t s, void* l0_begin,
-                             void* l0_end) {
+                             const int32_t* inverse, const void* sorted_src, bool src_rows,
+                             float* row_grads, void* table, int sgd_mode, int64_t total_rows,
+                             const int64_t* uniq, float lr, uint64_t seed, hipStream_t s,
+                             void* l0_begin, void* l0_end) {
   BwdWs wm = w;
   const int64_t num_bags = (int64_t)num_tables * batch;
 
-  const int4* src = sorted_src;
+  const void* src = sorted_src;
   if (!src) {
     // (u, bag) per sorted position from perm and inverse: expand the bags, then gather.
     const int64_t waves = (num_bags + 63) / 64;
@@ -932,24 +955,31 @@ hipError_t embbag_bwd_levels(const BwdWs& w, const void* grad, bool grad_bf16, i
     src = w.src;
   }
 
+  // row entries: the keys are the table rows (below total_rows) and need no uniq
   SgdTarget sgd{static_cast<char*>(table), total_rows,
-                (int64_t)dim * (sgd_mode >= 2 ? 2 : 4), uniq, lr, seed};
-  auto levels = [&](const auto& s0) {
+                (int64_t)dim * (sgd_mode >= 2 ? 2 : 4), src_rows ? nullptr : uniq, lr, seed};
+  const int64_t cap = src_rows ? total_rows : nnz;
+  auto levels = [&](const auto& s0) -> hipError_t {
     using S0 = std::decay_t<decltype(s0)>;
-    if (sgd_mode == 1)
-      return segreduce_levels<1, S0>(s0, nnz, dim, row_grads, sgd, wm, s, l0_begin, l0_end);
-    if (sgd_mode == 2)
-      return segreduce_levels<2, S0>(s0, nnz, dim, row_grads, sgd, wm, s, l0_begin, l0_end);
-    if (sgd_mode == 3)
-      return segreduce_levels<3, S0>(s0, nnz, dim, row_grads, sgd, wm, s, l0_begin, l0_end);
-    if (sgd_mode == 4)
-      return segreduce_levels<4, S0>(s0, nnz, dim, row_grads, sgd, wm, s, l0_begin, l0_end);
-    if (sgd_mode == 5)
-      return segreduce_levels<5, S0>(s0, nnz, dim, row_grads, sgd, wm, s, l0_begin, l0_end);
-    return segreduce_levels<0, S0>(s0, nnz, dim, row_grads, sgd, wm, s, l0_begin, l0_end);
+    switch (sgd_mode) {
+      case 1: return segreduce_levels<1, S0>(s0, nnz, cap, dim, row_grads, sgd, wm, s, l0_begin, l0_end);
+      case 2: return segreduce_levels<2, S0>(s0, nnz, cap, dim, row_grads, sgd, wm, s, l0_begin, l0_end);
+      case 3: return segreduce_levels<3, S0>(s0, nnz, cap, dim, row_grads, sgd, wm, s, l0_begin, l0_end);
+      case 4: return segreduce_levels<4, S0>(s0, nnz, cap, dim, row_grads, sgd, wm, s, l0_begin, l0_end);
+      case 5: return segreduce_levels<5, S0>(s0, nnz, cap, dim, row_grads, sgd, wm, s, l0_begin, l0_end);
+      default:
+        // row gradients are indexed by u, which row entries do not carry (the caller checks)
+        if constexpr (S0::kRows) return hipErrorInvalidValue;
+        else return segreduce_levels<0, S0>(s0, nnz, cap, dim, row_grads, sgd, wm, s, l0_begin, l0_end);
+    }
   };
-  const hipError_t e = grad_bf16 ? levels(L0SourceB{src, grad, sb, st, batch, num_bags})
-                                 : levels(L0Source{src, grad, sb, st, batch, num_bags});
+  hipError_t e;
+  if (src_rows)
+    e = grad_bf16 ? levels(L0SourceT<true, true>{src, grad, sb, st, batch, num_bags})
+                  : levels(L0SourceT<false, true>{src, grad, sb, st, batch, num_bags});
+  else
+    e = grad_bf16 ? levels(L0SourceB{src, grad, sb, st, batch, num_bags})
+                  : levels(L0Source{src, grad, sb, st, batch, num_bags});
   if (e != hipSuccess) return e;
   return hipGetLastError();
 }
@@ -958,8 +988,9 @@ hipError_t embbag_bwd_levels(const BwdWs& w, const void* grad, bool grad_bf16, i
 hipError_t launch_embbag_bwd(const void* grad, bool grad_bf16, int64_t sb, int64_t st,
                              const int64_t* offsets,
                              int64_t batch, int32_t num_tables, int dim, int64_t nnz,
-                             const int32_t* perm, const int32_t* inverse, const int4* sorted_src,
-                             const int32_t* num_unique, float* row_grads, void* table,
+                             const int32_t* perm, const int32_t* inverse, const void* sorted_src,
+                             bool src_rows, const int32_t* num_unique, float* row_grads,
+                             void* table,
                              int sgd_mode, int64_t total_rows, const int64_t* uniq, float lr,
                              uint64_t seed, void* workspace, hipStream_t s, void* l0_begin,
                              void* l0_end) {
@@ -970,14 +1001,14 @@ hipError_t launch_embbag_bwd(const void* grad, bool grad_bf16, int64_t sb, int64
   }
   BwdWs w = carve(workspace, nnz, dim);
   return embbag_bwd_levels(w, grad, grad_bf16, sb, st, offsets, batch, num_tables, dim, nnz, perm,
-                           inverse, sorted_src, row_grads, table, sgd_mode, total_rows, uniq, lr,
-                           seed, s, l0_begin, l0_end);
+                           inverse, sorted_src, src_rows, row_grads, table, sgd_mode, total_rows,
+                           uniq, lr, seed, s, l0_begin, l0_end);
 }
 
 hipError_t launch_embbag_bwd_noalloc(const void* grad, bool grad_bf16, int64_t sb, int64_t st,
                                      const int64_t* offsets, int64_t batch, int32_t num_tables,
-                                     int dim, int64_t nnz, const int4* sorted_src,
-                                     float* row_grads, void* table, int sgd_mode,
+                                     int dim, int64_t nnz, const void* sorted_src,
+                                     bool src_rows, float* row_grads, void* table, int sgd_mode,
                                      int64_t total_rows, const int64_t* uniq, float lr,
                                      uint64_t seed, hipStream_t s) {
   if (nnz == 0) return hipSuccess;
@@ -986,8 +1017,8 @@ hipError_t launch_embbag_bwd_noalloc(const void* grad, bool grad_bf16, int64_t s
   if (e != hipSuccess) return e;
   BwdWs w = carve_carries(base, nnz, dim);   // fits: the caller checked the size
   return embbag_bwd_levels(w, grad, grad_bf16, sb, st, offsets, batch, num_tables, dim, nnz,
-                           nullptr, nullptr, sorted_src, row_grads, table, sgd_mode, total_rows,
-                           uniq, lr, seed, s, nullptr, nullptr);
+                           nullptr, nullptr, sorted_src, src_rows, row_grads, table, sgd_mode,
+                           total_rows, uniq, lr, seed, s, nullptr, nullptr);
 }
 
 }  // namespace ctr

@@ -50,10 +50,11 @@ int32_t unique_into(const ctr_step_t* d, int set, void* stream, int ws = 0) {
                           d->num_tables, d->row_base, d->total_rows, d->max_table_rows, 0,
                           d->uniq[set],
                           d->inverse[set], d->num_unique[set], d->perm[set], d->seg_offsets[set],
-                          d->sorted_src[set], wsp, &wsb, stream);
+                          d->sorted_src[set], d->src_layout, wsp, &wsb, stream);
   return ctr_unique_ids(d->indices, d->index_type, d->nnz, nullptr, 0, 0, nullptr, 0, 0,
                         d->key_modulus, d->uniq[set], d->inverse[set], d->num_unique[set],
-                        d->perm[set], d->seg_offsets[set], d->sorted_src[set], wsp, &wsb, stream);
+                        d->perm[set], d->seg_offsets[set], d->sorted_src[set], d->src_layout,
+                        wsp, &wsb, stream);
 }
 
 // The stages before the unique may fork (pooling, and for the batch-matrix step the gather).
@@ -109,7 +110,8 @@ int32_t sgd_part(const ctr_step_t* d, int set, int64_t k, hipStream_t s, void* m
   const int32_t tables = pooled ? d->num_tables : 1;
   const bool sr = d->rounding == CTR_ROUND_STOCHASTIC;
   return ctr::embbag_bwd_sgd_marked(grad, gdt, sb, st, d->offsets, batch, tables, d->nnz,
-                                    d->sorted_src[set], d->num_unique[set], d->table, d->dtype,
+                                    d->sorted_src[set], d->src_layout, d->num_unique[set],
+                                    d->table, d->dtype,
                                     d->total_rows, d->dim, d->uniq[set], d->lr, d->rounding,
                                     sr ? ctr_sr_step_seed(d->sr_seed, k) : 0, d->row_grads,
                                     d->ws_bwd, &wsb, s, mark_begin, mark_end);

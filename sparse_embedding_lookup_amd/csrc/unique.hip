@@ -532,7 +532,8 @@ __global__ __launch_bounds__(1024) void heads_scan_kernel(uint32_t* __restrict__
 }
 
 // sorted_src[p] = (distinct-row index of position p, bag of its occurrence, key as two
-// words); bag_of gives the bag, and without bags the occurrence is its own bag.  Every load of the tile is issued first (keys, the key before each position,
+// words), or with rows (key, bag) as int32 pairs; bag_of gives the bag, and without bags the
+// occurrence is its own bag.  Every load of the tile is issued first (keys, the key before each position,
 // occurrence, then the bags through the occurrences; and, when FUSED, the head counts of the
 // earlier tiles), then one barrier publishes the per-round wave head counts.
 // FUSED: few tiles, so the block sums the head counts of the tiles before it itself, and
@@ -547,7 +548,7 @@ __global__ __launch_bounds__(kThreads) void unique_finalize_kernel(
     const K* __restrict__ sk, const uint32_t* __restrict__ sv, const void* __restrict__ bag_of,
     int64_t n, uint64_t flip, const uint32_t* __restrict__ tile_heads, int64_t ntiles,
     int64_t* __restrict__ uniq, int32_t* __restrict__ inverse, int32_t* __restrict__ seg_offsets,
-    int4* __restrict__ sorted_src, int32_t* __restrict__ num_unique,
+    void* __restrict__ sorted_src, bool rows, int32_t* __restrict__ num_unique,
     const int64_t* __restrict__ row_base, int num_tables, int64_t batch, int seg_bits) {
   __shared__ uint32_t wcnt[kFinRounds][4];
   __shared__ uint32_t wtile[2][4];
@@ -649,7 +650,11 @@ __global__ __launch_bounds__(kThreads) void unique_finalize_kernel(
           }
           bg += (uint32_t)((int64_t)lo * batch);
         }
-        sorted_src[p] = make_int4((int32_t)r, (int32_t)bg, (int32_t)kk, (int32_t)(kk >> 32));
+        if (rows)
+          static_cast<int2*>(sorted_src)[p] = make_int2((int32_t)kk, (int32_t)bg);
+        else
+          static_cast<int4*>(sorted_src)[p] =
+              make_int4((int32_t)r, (int32_t)bg, (int32_t)kk, (int32_t)(kk >> 32));
       }
     }
   }
@@ -793,7 +798,8 @@ hipError_t unique_impl(const void* ids, bool ids64, int64_t n, const int64_t* of
                        int64_t batch, int32_t num_tables, const int64_t* row_base,
                        int64_t modulus, int key_bits, int seg_bits, uint64_t flip,
                        int64_t* uniq, int32_t* inverse, int32_t* num_unique, int32_t* perm,
-                       int32_t* seg_offsets, int4* sorted_src, UniqueWs& w, hipStream_t s) {
+                       int32_t* seg_offsets, void* sorted_src, bool src_rows, UniqueWs& w,
+                       hipStream_t s) {
   const bool bags = offsets != nullptr && sorted_src != nullptr;
   // 16-bit sample indices for the bags when the table can be told from the key
   const bool b16 = bags && row_base != nullptr && batch <= 65536 &&
@@ -867,7 +873,7 @@ hipError_t unique_impl(const void* ids, bool ids64, int64_t n, const int64_t* of
 #define CTR_FIN(FU, B)                                                                     \
   unique_finalize_kernel<K, FU, B><<<(unsigned)ftiles, kThreads, 0, s>>>(                  \
       sk, sv, sb, n, flip, w.tile_heads, ftiles, uniq, inverse, seg_offsets, sorted_src,   \
-      num_unique, row_base, num_tables, batch, seg_bits)
+      src_rows, num_unique, row_base, num_tables, batch, seg_bits)
   if (ftiles <= kFusedHeadTiles) {
     if (b16) CTR_FIN(true, true); else CTR_FIN(true, false);
   } else {
@@ -886,8 +892,8 @@ hipError_t launch_unique(const void* ids, bool ids64, int64_t n, const int64_t* 
                          int64_t batch, int32_t num_tables, const int64_t* row_base,
                          int64_t modulus, int key_bits, int seg_bits, bool key_signed,
                          int64_t* uniq, int32_t* inverse, int32_t* num_unique, int32_t* perm,
-                         int32_t* seg_offsets, int4* sorted_src, void* workspace,
-                         hipStream_t s) {
+                         int32_t* seg_offsets, void* sorted_src, bool src_rows,
+                         void* workspace, hipStream_t s) {
   if (n == 0) {
     unique_empty_kernel<<<1, 64, 0, s>>>(num_unique, seg_offsets);
     return hipGetLastError();
@@ -899,10 +905,10 @@ hipError_t launch_unique(const void* ids, bool ids64, int64_t n, const int64_t* 
   if (seg_bits || (!key_signed && key_bits <= 32))
     return unique_impl<uint32_t>(ids, ids64, n, offsets, batch, num_tables, row_base, modulus,
                                  key_bits, seg_bits, flip, uniq, inverse, num_unique, perm,
-                                 seg_offsets, sorted_src, w, s);
+                                 seg_offsets, sorted_src, src_rows, w, s);
   return unique_impl<uint64_t>(ids, ids64, n, offsets, batch, num_tables, row_base, modulus,
                                key_bits, 0, flip, uniq, inverse, num_unique, perm, seg_offsets,
-                               sorted_src, w, s);
+                               sorted_src, src_rows, w, s);
 }
 
 }  // namespace ctr

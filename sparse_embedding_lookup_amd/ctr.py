@@ -42,6 +42,7 @@ CTR_SCHEDULE_SERIAL, CTR_SCHEDULE_PIPELINED, CTR_SCHEDULE_PIPELINED_EARLY = 0, 1
 CTR_SCHEDULE_PIPELINED_OVERLAP = 3
 CTR_ROUND_NEAREST, CTR_ROUND_STOCHASTIC = 0, 1
 CTR_MARK_POOLING, CTR_MARK_BACKWARD = 0, 1
+CTR_SRC_FULL, CTR_SRC_ROWS = 0, 1
 
 
 class CtrStep(ctypes.Structure):
@@ -61,7 +62,8 @@ class CtrStep(ctypes.Structure):
                 ("sr_seed", ctypes.c_uint64), ("grad_dtype", ctypes.c_int32),
                 ("ws_unique2", _P), ("ws_unique2_bytes", ctypes.c_size_t),
                 ("mark_stage", ctypes.c_int32), ("max_table_rows", ctypes.c_int64),
-                ("ws_pool", _P), ("ws_pool_bytes", ctypes.c_size_t)]
+                ("ws_pool", _P), ("ws_pool_bytes", ctypes.c_size_t),
+                ("src_layout", ctypes.c_int32)]
 
 _lib = None
 
@@ -92,13 +94,13 @@ def load() -> ctypes.CDLL:
         "ctr_version": (i32, []),
         "ctr_status_string": (ctypes.c_char_p, [i32]),
         "ctr_last_error_message": (ctypes.c_char_p, []),
-        "ctr_unique_ids": (i32, [P, i32, i64, P, i64, i32, P, i64, i64, i64, P, P, P, P, P, P, P,
-                                 PS, P]),
+        "ctr_unique_ids": (i32, [P, i32, i64, P, i64, i32, P, i64, i64, i64, P, P, P, P, P, P,
+                                 i32, P, PS, P]),
         "ctr_gather_rows": (i32, [P, i32, i64, i32, P, P, i64, P, P]),
         "ctr_embbag_fwd": (i32, [P, i32, i64, i32, P, i32, P, i32, i64, P, i64, P, i64, i64, P,
                                  PS, P]),
         "ctr_embbag_bwd": (i32, [P, i64, i64, P, i64, i32, i32, i64, P, P, P, P, P, P, PS, P]),
-        "ctr_embbag_bwd_sgd": (i32, [P, i32, i64, i64, P, i64, i32, i64, P, P, P, i32, i64,
+        "ctr_embbag_bwd_sgd": (i32, [P, i32, i64, i64, P, i64, i32, i64, P, i32, P, P, i32, i64,
                                      i32, P, f32, i32, u64, P, P, PS, P]),
         "ctr_sparse_sgd": (i32, [P, i32, i64, i32, P, P, i64, P, f32, i32, u64, P]),
         "ctr_sr_step_seed": (u64, [u64, i64]),
@@ -108,8 +110,8 @@ def load() -> ctypes.CDLL:
         "ctr_dot_interaction_gram_bwd": (i32, [P, P, i64, i64, i32, i32, i32, i32, P, P]),
         "ctr_fm_interaction_fwd": (i32, [P, i64, i32, i32, P, P]),
         "ctr_fm_interaction_bwd": (i32, [P, P, i64, i32, i32, P, P]),
-        "ctr_embbag_bwd_sgd_noalloc": (i32, [P, i32, i64, i64, P, i64, i32, i64, P, P, P, i32,
-                                             i64, i32, P, f32, i32, u64, P, P]),
+        "ctr_embbag_bwd_sgd_noalloc": (i32, [P, i32, i64, i64, P, i64, i32, i64, P, i32, P, P,
+                                             i32, i64, i32, P, f32, i32, u64, P, P]),
         "ctr_embbag_bwd_noalloc_scratch_bytes": (sz, [i64, i32]),
         "ctr_noalloc_scratch_capacity": (sz, []),
         "ctr_dict_build": (i32, [P, P, P, i64, P, i64, P, P]),
@@ -140,6 +142,16 @@ def load() -> ctypes.CDLL:
 
 def _ptr(t: Optional[torch.Tensor]):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def src_layout(sorted_src: Optional[torch.Tensor]) -> int:
+    """The layout code of a sorted_src tensor: int32 [n, 4] quadruples (CTR_SRC_FULL) or
+    [n, 2] row entries (CTR_SRC_ROWS)."""
+    if sorted_src is None or sorted_src.shape[-1] == 4:
+        return CTR_SRC_FULL
+    if sorted_src.shape[-1] == 2:
+        return CTR_SRC_ROWS
+    raise ValueError("sorted_src must be int32 [n, 4] or [n, 2], not %s" % (tuple(sorted_src.shape),))
 
 
 def _stream(stream=None):
@@ -201,8 +213,8 @@ def unique_workspace_bytes(n: int) -> int:
     """Workspace of ctr_unique_ids for n occurrences (the library's two-call query)."""
     wsb = ctypes.c_size_t(0)
     _check("ctr_unique_ids", load().ctr_unique_ids(None, CTR_I64, n, None, 0, 0, None, 0, 0, 0,
-                                                   None, None, None, None, None, None, None,
-                                                   ctypes.byref(wsb), None))
+                                                   None, None, None, None, None, None,
+                                                   CTR_SRC_FULL, None, ctypes.byref(wsb), None))
     return wsb.value
 
 
@@ -236,7 +248,8 @@ def ctr_unique_ids(ids: torch.Tensor, *, offsets: Optional[torch.Tensor] = None,
     library then leaves them out, and the sort carries no occurrence payload when none of
     the three is asked for and the bags ride along); ``sorted_src``
     (int32 [n, 4], 16-byte aligned) receives (distinct-row index, bag, key low word, key high
-    word) for every sorted position."""
+    word) for every sorted position, or as int32 [n, 2] (8-byte aligned) the row entries
+    (key, bag) of CTR_SRC_ROWS."""
     n = ids.numel()
     dev = ids.device
     if out is not None:
@@ -254,7 +267,7 @@ def ctr_unique_ids(ids: torch.Tensor, *, offsets: Optional[torch.Tensor] = None,
     ws = workspace
     wsb = ctypes.c_size_t(ws.numel())
     full = args + (_ptr(uniq), _ptr(inv), _ptr(nu), _ptr(perm), _ptr(seg), _ptr(sorted_src),
-                   _ptr(ws), ctypes.byref(wsb))
+                   src_layout(sorted_src), _ptr(ws), ctypes.byref(wsb))
     res = (uniq[:n], (inv[:n] if inv is not None else None), nu,
            (perm[:n] if perm is not None else None), seg)
     return _run("ctr_unique_ids", full, stream, prepare, res)
@@ -339,16 +352,19 @@ def ctr_embbag_bwd_sgd(grad: torch.Tensor, grad_stride_b: int, grad_stride_t: in
                        stream=None, prepare: bool = False):
     """Per-row gradient sums applied straight to the table as the sparse SGD update, rounded
     by ``rounding`` (stochastic: random bits from ``seed``).  The gradient type is the
-    tensor's (fp32 or bf16); table None: row sums into row_grads only (dim then required)."""
+    tensor's (fp32 or bf16); table None: row sums into row_grads only (dim then required).
+    ``sorted_src`` of shape [n, 2] holds row entries (CTR_SRC_ROWS: uniq unused, no
+    row_grads)."""
     total_rows, d = (0, dim) if table is None else table.shape
     if workspace is None:
         workspace = _workspace(embbag_bwd_workspace_bytes(nnz, d), grad.device)
     wsb = ctypes.c_size_t(workspace.numel())
     args = (_ptr(grad), _dtype_code(grad), grad_stride_b, grad_stride_t, _ptr(offsets), batch,
-            num_tables, nnz, _ptr(sorted_src), _ptr(num_unique), _ptr(table),
-            CTR_F32 if table is None else _dtype_code(table), total_rows, d, _ptr(uniq),
-            ctypes.c_float(lr), rounding, ctypes.c_uint64(seed & 0xFFFFFFFFFFFFFFFF),
-            _ptr(row_grads), _ptr(workspace), ctypes.byref(wsb))
+            num_tables, nnz, _ptr(sorted_src), src_layout(sorted_src), _ptr(num_unique),
+            _ptr(table), CTR_F32 if table is None else _dtype_code(table), total_rows, d,
+            _ptr(uniq), ctypes.c_float(lr), rounding,
+            ctypes.c_uint64(seed & 0xFFFFFFFFFFFFFFFF), _ptr(row_grads), _ptr(workspace),
+            ctypes.byref(wsb))
     return _run("ctr_embbag_bwd_sgd", args, stream, prepare, row_grads)
 
 
@@ -363,10 +379,10 @@ def ctr_embbag_bwd_sgd_noalloc(grad: torch.Tensor, grad_stride_b: int, grad_stri
     reduce-by-key carries (table None: row sums into row_grads only; dim then required)."""
     total_rows, d = (0, dim) if table is None else table.shape
     args = (_ptr(grad), _dtype_code(grad), grad_stride_b, grad_stride_t, _ptr(offsets), batch,
-            num_tables, nnz, _ptr(sorted_src), _ptr(num_unique), _ptr(table),
-            CTR_F32 if table is None else _dtype_code(table), total_rows, d, _ptr(uniq),
-            ctypes.c_float(lr), rounding, ctypes.c_uint64(seed & 0xFFFFFFFFFFFFFFFF),
-            _ptr(row_grads))
+            num_tables, nnz, _ptr(sorted_src), src_layout(sorted_src), _ptr(num_unique),
+            _ptr(table), CTR_F32 if table is None else _dtype_code(table), total_rows, d,
+            _ptr(uniq), ctypes.c_float(lr), rounding,
+            ctypes.c_uint64(seed & 0xFFFFFFFFFFFFFFFF), _ptr(row_grads))
     return _run("ctr_embbag_bwd_sgd_noalloc", args, stream, prepare, row_grads)
 
 

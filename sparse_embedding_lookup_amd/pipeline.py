@@ -37,7 +37,8 @@ class FrontEnd:
     def __init__(self, w: Workload, device="cuda", table: Optional[torch.Tensor] = None,
                  fused: bool = True, keep_grads: bool = False, pipelined: bool = False,
                  rounding: str = "nearest", sr_seed: int = SR_SEED, pad_r: bool = False,
-                 fused_fwd: bool = False, lean_unique: bool = False):
+                 fused_fwd: bool = False, lean_unique: bool = False,
+                 src_rows: Optional[bool] = None):
         """fused: the backward applies the sparse SGD as each row gradient completes
         (ctr_embbag_bwd_sgd); otherwise ctr_embbag_bwd then ctr_sparse_sgd.  keep_grads: also
         keep the per-row gradients in self.row_grads (always kept when not fused).
@@ -54,7 +55,10 @@ class FrontEnd:
         then ctr_dot_interaction_fwd (pooled-interaction workloads only).
         lean_unique: the pooled step's unique (Python-driven and native) produces only what
         its backward reads (distinct rows, their count, sorted_src): no inverse map,
-        permutation or segment offsets, and no occurrence payload through the sort."""
+        permutation or segment offsets, and no occurrence payload through the sort.
+        src_rows: sorted_src holds 8-byte row entries (CTR_SRC_ROWS) instead of 16-byte
+        (u, bag, key) quadruples; only for the fused update without kept gradients, which is
+        also the default (None) then."""
         assert rounding in ("nearest", "stochastic")
         assert rounding == "nearest" or w.dtype in ("bf16", "f16"), \
             "stochastic rounding: bf16 or fp16 tables"
@@ -68,6 +72,11 @@ class FrontEnd:
         self.fused = fused
         self.fused_fwd = bool(fused_fwd and w.interaction)
         self.keep_grads = keep_grads or not fused
+        if src_rows is None:
+            src_rows = self.fused and not self.keep_grads
+        assert not src_rows or (self.fused and not self.keep_grads), \
+            "row entries serve the fused update without row gradients"
+        self.src_rows = src_rows
         self.device = torch.device(device)
         self.compute = ctr.CTR_BF16 if w.compute == "bf16" else ctr.CTR_F32
         tdt = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}[w.dtype]
@@ -110,7 +119,8 @@ class FrontEnd:
                                   dtype=torch.uint8, device=dv)
         self.ws_pool = torch.zeros(max(ctr.embbag_fwd_workspace_bytes(max(n, 1), d), 256),
                                    dtype=torch.uint8, device=dv)
-        self._sets = [self._unique_buffers(n, dv) for _ in range(3 if pipelined else 1)]
+        self._sets = [self._unique_buffers(n, dv, 2 if src_rows else 4)
+                      for _ in range(3 if pipelined else 1)]
         self._calls = []
         self.side = None
         self._k = 0
@@ -121,13 +131,14 @@ class FrontEnd:
         self._use_set(0)
 
     @staticmethod
-    def _unique_buffers(n, dv):
+    def _unique_buffers(n, dv, src_words):
         return dict(uniq=torch.empty(max(n, 1), dtype=torch.int64, device=dv),
                     inverse=torch.empty(max(n, 1), dtype=torch.int32, device=dv),
                     num_unique=torch.zeros(1, dtype=torch.int32, device=dv),
                     perm=torch.empty(max(n, 1), dtype=torch.int32, device=dv),
                     seg=torch.empty(n + 1, dtype=torch.int32, device=dv),
-                    sorted_src=torch.empty((max(n, 1), 4), dtype=torch.int32, device=dv))
+                    sorted_src=torch.empty((max(n, 1), src_words), dtype=torch.int32,
+                                           device=dv))
 
     def _use_set(self, i):
         """Point the unique outputs, and the prepared calls that use them, at set i."""
@@ -456,6 +467,7 @@ class FrontEnd:
             d.perm[i] = None if lean else P(b["perm"])
             d.seg_offsets[i] = None if lean else P(b["seg"])
             d.sorted_src[i] = P(b["sorted_src"])
+        d.src_layout = ctr.CTR_SRC_ROWS if self.src_rows else ctr.CTR_SRC_FULL
         self._native = d
         self._ev_fork, self._ev_join = torch.cuda.Event(), torch.cuda.Event()
         self._ev_fork.record()          # torch creates the HIP event on its first record

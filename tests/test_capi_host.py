@@ -60,29 +60,29 @@ def test_unique_workspace_query_and_bad_args():
     lib = _lib()
     wsb = ctypes.c_size_t(0)
     assert lib.ctr_unique_ids(None, 1, 1000, None, 0, 0, None, 0, 0, 0, None, None, None, None,
-                              None, None, None, ctypes.byref(wsb), None) == ctr.CTR_OK
+                              None, None, 0, None, ctypes.byref(wsb), None) == ctr.CTR_OK
     assert wsb.value >= 1000 * 24
     bad = ctypes.c_size_t(10)
     st = lib.ctr_unique_ids(FAKE, 1, 1000, None, 0, 0, None, 0, 0, 0, FAKE, FAKE, FAKE, None, None,
-                            None, FAKE, ctypes.byref(bad), None)
+                            None, 0, FAKE, ctypes.byref(bad), None)
     assert st == ctr.CTR_ERR_WORKSPACE_TOO_SMALL
     big = ctypes.c_size_t(wsb.value)
     st = lib.ctr_unique_ids(FAKE, 1, 1000, None, 0, 0, None, 0, 0, 0, FAKE, FAKE, FAKE, None, None,
-                            None, MISALIGNED, ctypes.byref(big), None)
+                            None, 0, MISALIGNED, ctypes.byref(big), None)
     assert st == ctr.CTR_ERR_UNSUPPORTED and b"aligned" in lib.ctr_last_error_message()
     assert lib.ctr_unique_ids(FAKE, 1, -1, None, 0, 0, None, 0, 0, 0, None, None, None, None, None,
-                              None, None, ctypes.byref(wsb), None) == ctr.CTR_ERR_INVALID_ARGUMENT
+                              None, 0, None, ctypes.byref(wsb), None) == ctr.CTR_ERR_INVALID_ARGUMENT
     assert lib.ctr_unique_ids(FAKE, 1, 2 ** 31, None, 0, 0, None, 0, 0, 0, None, None, None, None,
-                              None, None, None, ctypes.byref(wsb), None) == ctr.CTR_ERR_INVALID_ARGUMENT
+                              None, None, 0, None, ctypes.byref(wsb), None) == ctr.CTR_ERR_INVALID_ARGUMENT
     assert lib.ctr_unique_ids(FAKE, 7, 10, None, 0, 0, None, 0, 0, 0, None, None, None, None, None,
-                              None, None, ctypes.byref(wsb), None) == ctr.CTR_ERR_INVALID_ARGUMENT
+                              None, 0, None, ctypes.byref(wsb), None) == ctr.CTR_ERR_INVALID_ARGUMENT
     # row_base without offsets
     assert lib.ctr_unique_ids(FAKE, 1, 10, None, 4, 2, FAKE, 100, 0, 0, None, None, None, None, None,
-                              None, None, ctypes.byref(wsb), None) == ctr.CTR_ERR_INVALID_ARGUMENT
+                              None, 0, None, ctypes.byref(wsb), None) == ctr.CTR_ERR_INVALID_ARGUMENT
     assert b"offsets" in lib.ctr_last_error_message()
     # a negative largest-table hint
     assert lib.ctr_unique_ids(FAKE, 1, 10, FAKE, 4, 2, FAKE, 100, -1, 0, None, None, None, None,
-                              None, None, None, ctypes.byref(wsb), None) == \
+                              None, None, 0, None, ctypes.byref(wsb), None) == \
         ctr.CTR_ERR_INVALID_ARGUMENT
 
 
@@ -240,23 +240,23 @@ def test_rounding_argument_bad_args():
     assert b"rounding" in lib.ctr_last_error_message()
     # fp16 tables take both roundings (the query of the fused backward answers)
     wsb = ctypes.c_size_t(0)
-    assert lib.ctr_embbag_bwd_sgd(None, ctr.CTR_F32, 64, 0, None, 10, 1, 100, None, None, FAKE,
+    assert lib.ctr_embbag_bwd_sgd(None, ctr.CTR_F32, 64, 0, None, 10, 1, 100, None, 0, None, FAKE,
                                   ctr.CTR_F16, 1000, 16, None, ctypes.c_float(0.01), SR, s0,
                                   None, None, ctypes.byref(wsb), None) == ctr.CTR_OK
     assert wsb.value > 0
     wsb = ctypes.c_size_t(0)
     bwd = lib.ctr_embbag_bwd_sgd
-    st = bwd(FAKE, ctr.CTR_F32, 64, 0, FAKE, 10, 1, 100, FAKE, FAKE, FAKE, ctr.CTR_F32, 1000, 16,
+    st = bwd(FAKE, ctr.CTR_F32, 64, 0, FAKE, 10, 1, 100, FAKE, 0, FAKE, FAKE, ctr.CTR_F32, 1000, 16,
              FAKE, ctypes.c_float(0.01), SR, s0, None, None, ctypes.byref(wsb), None)
     assert st == ctr.CTR_ERR_UNSUPPORTED
-    assert bwd(FAKE, ctr.CTR_F32, 64, 0, FAKE, 10, 1, 100, FAKE, FAKE, FAKE, ctr.CTR_BF16, 1000,
+    assert bwd(FAKE, ctr.CTR_F32, 64, 0, FAKE, 10, 1, 100, FAKE, 0, FAKE, FAKE, ctr.CTR_BF16, 1000,
                16, FAKE, ctypes.c_float(0.01), 9, s0, None, None, ctypes.byref(wsb), None) == \
         ctr.CTR_ERR_INVALID_ARGUMENT
-    assert bwd(FAKE, 4, 64, 0, FAKE, 10, 1, 100, FAKE, FAKE, FAKE, ctr.CTR_BF16, 1000, 16, FAKE,
+    assert bwd(FAKE, 4, 64, 0, FAKE, 10, 1, 100, FAKE, 0, FAKE, FAKE, ctr.CTR_BF16, 1000, 16, FAKE,
                ctypes.c_float(0.01), 0, s0, None, None, ctypes.byref(wsb), None) == \
         ctr.CTR_ERR_INVALID_ARGUMENT
     assert b"grad_dtype" in lib.ctr_last_error_message()
-    assert bwd(None, ctr.CTR_F32, 64, 0, None, 10, 1, 100, None, None, FAKE, ctr.CTR_BF16, 1000,
+    assert bwd(None, ctr.CTR_F32, 64, 0, None, 10, 1, 100, None, 0, None, FAKE, ctr.CTR_BF16, 1000,
                16, None, ctypes.c_float(0.01), SR, s0, None, None, ctypes.byref(wsb), None) == \
         ctr.CTR_OK
     assert wsb.value > 0                          # the workspace query of ctr_embbag_bwd
@@ -431,6 +431,58 @@ def test_dense_and_head_bad_args():
         ctr.CTR_ERR_INVALID_ARGUMENT
 
 
+def test_row_entry_layout_rejections():
+    """CTR_SRC_ROWS (8-byte (row, bag) entries): an unknown layout, keys that need more than
+    31 bits, 8-byte misalignment, and a backward that would need u (row gradients, no table)
+    are rejected before any launch."""
+    lib = _lib()
+    wsb = ctypes.c_size_t(0)
+    assert lib.ctr_unique_ids(None, 1, 1000, None, 0, 0, None, 0, 0, 0, None, None, None, None,
+                              None, None, 0, None, ctypes.byref(wsb), None) == ctr.CTR_OK
+    big = ctypes.c_size_t(wsb.value)
+    uq = lambda *a: lib.ctr_unique_ids(*a, FAKE, ctypes.byref(big), None)
+    # (ids, id_type, n, offsets, batch, T, row_base, total_rows, max_rows, modulus, uniq, inv,
+    #  num_unique, perm, seg, sorted_src, src_layout)
+    assert uq(FAKE, 1, 1000, None, 0, 0, None, 0, 0, 0, FAKE, FAKE, FAKE, None, None, FAKE,
+              5) == ctr.CTR_ERR_INVALID_ARGUMENT
+    assert b"src_layout" in lib.ctr_last_error_message()
+    # raw int64 keys (no row_base, no modulus) do not fit the 32-bit key of a row entry
+    assert uq(FAKE, 1, 1000, None, 0, 0, None, 0, 0, 0, FAKE, FAKE, FAKE, None, None, FAKE,
+              ctr.CTR_SRC_ROWS) == ctr.CTR_ERR_UNSUPPORTED
+    assert uq(FAKE, 1, 1000, None, 0, 0, None, 0, 0, (1 << 31) + 1, FAKE, FAKE, FAKE, None,
+              None, FAKE, ctr.CTR_SRC_ROWS) == ctr.CTR_ERR_UNSUPPORTED
+    assert uq(FAKE, 1, 1000, FAKE, 4, 2, FAKE, 1 << 31, 0, 0, FAKE, FAKE, FAKE, None, None,
+              FAKE, ctr.CTR_SRC_ROWS) == ctr.CTR_ERR_UNSUPPORTED
+    assert uq(FAKE, 1, 1000, None, 0, 0, None, 0, 0, 1000, FAKE, FAKE, FAKE, None, None,
+              MISALIGNED, ctr.CTR_SRC_ROWS) == ctr.CTR_ERR_UNSUPPORTED
+    assert b"8-byte" in lib.ctr_last_error_message()
+    # the backward: (grad, grad_dtype, sb, st, offsets, batch, T, nnz, sorted_src, src_layout,
+    #  num_unique, table, dtype, total_rows, dim, uniq, lr, rounding, seed, row_grads, ws, wsb)
+    lr, s0 = ctypes.c_float(0.01), ctypes.c_uint64(0)
+    wsb = ctypes.c_size_t(0)
+    assert lib.ctr_embbag_bwd_sgd(None, ctr.CTR_F32, 64, 0, None, 10, 1, 100, None,
+                                  ctr.CTR_SRC_ROWS, None, FAKE, ctr.CTR_F32, 1000, 16, None, lr,
+                                  0, s0, None, None, ctypes.byref(wsb), None) == ctr.CTR_OK
+    big = ctypes.c_size_t(wsb.value)
+    bwd = lambda *a: lib.ctr_embbag_bwd_sgd(*a, FAKE, ctypes.byref(big), None)
+    assert bwd(FAKE, ctr.CTR_F32, 64, 0, FAKE, 10, 1, 100, FAKE, 3, FAKE, FAKE, ctr.CTR_F32,
+               1000, 16, None, lr, 0, s0, None) == ctr.CTR_ERR_INVALID_ARGUMENT
+    assert b"src_layout" in lib.ctr_last_error_message()
+    # row gradients are indexed by u, which row entries do not carry
+    assert bwd(FAKE, ctr.CTR_F32, 64, 0, FAKE, 10, 1, 100, FAKE, ctr.CTR_SRC_ROWS, FAKE, FAKE,
+               ctr.CTR_F32, 1000, 16, None, lr, 0, s0, FAKE) == ctr.CTR_ERR_INVALID_ARGUMENT
+    assert b"row_grads" in lib.ctr_last_error_message()
+    assert bwd(FAKE, ctr.CTR_F32, 64, 0, FAKE, 10, 1, 100, FAKE, ctr.CTR_SRC_ROWS, FAKE, None,
+               ctr.CTR_F32, 1000, 16, None, lr, 0, s0, FAKE) == ctr.CTR_ERR_INVALID_ARGUMENT
+    assert bwd(FAKE, ctr.CTR_F32, 64, 0, FAKE, 10, 1, 100, MISALIGNED, ctr.CTR_SRC_ROWS, FAKE,
+               FAKE, ctr.CTR_F32, 1000, 16, None, lr, 0, s0, None) == ctr.CTR_ERR_UNSUPPORTED
+    assert b"8-byte" in lib.ctr_last_error_message()
+    # the quadruple layout still needs uniq with a table
+    assert bwd(FAKE, ctr.CTR_F32, 64, 0, FAKE, 10, 1, 100, FAKE, ctr.CTR_SRC_FULL, FAKE, FAKE,
+               ctr.CTR_F32, 1000, 16, None, lr, 0, s0, None) == ctr.CTR_ERR_INVALID_ARGUMENT
+    assert b"uniq" in lib.ctr_last_error_message()
+
+
 def test_noalloc_backward_limits_and_rejections():
     """The backward that allocates nothing: a fixed per-GPU scratch (64 MiB), a size query,
     and batches beyond it rejected on the host before any launch (fake device pointers)."""
@@ -440,7 +492,7 @@ def test_noalloc_backward_limits_and_rejections():
     assert 0 < small < 64 << 20
     assert lib.ctr_embbag_bwd_noalloc_scratch_bytes(67_000_000, 128) > 64 << 20
     assert lib.ctr_embbag_bwd_noalloc_scratch_bytes(-1, 64) == ctypes.c_size_t(-1).value
-    args = (FAKE, 1, 65 * 128, 128, FAKE, 32768, 64, 67_000_000, FAKE, FAKE, FAKE, 1,
+    args = (FAKE, 1, 65 * 128, 128, FAKE, 32768, 64, 67_000_000, FAKE, 0, FAKE, FAKE, 1,
             256_000_000, 128, FAKE, ctypes.c_float(0.01), 0, ctypes.c_uint64(0), None, None)
     assert lib.ctr_embbag_bwd_sgd_noalloc(*args) == 2          # CTR_ERR_UNSUPPORTED
     assert b"scratch" in lib.ctr_last_error_message()
@@ -448,7 +500,7 @@ def test_noalloc_backward_limits_and_rejections():
     bad[1] = 7                                                 # unknown gradient dtype
     assert lib.ctr_embbag_bwd_sgd_noalloc(*bad) == 1
     bad = list(args)
-    bad[16] = 9                                                # unknown rounding
+    bad[17] = 9                                                # unknown rounding
     assert lib.ctr_embbag_bwd_sgd_noalloc(*bad) == 1
 
 

@@ -220,6 +220,43 @@ def test_unique_lean_outputs_match_the_full_call(name, hint):
     np.testing.assert_array_equal(s1[:, 0], oi[op])
 
 
+@pytest.mark.parametrize("name,hint", [("tiny_tables", False), ("small_tables", False),
+                                       ("tensornet_mod", False), ("all_equal", False),
+                                       ("hot_row_sprinkled", False), ("large_t8_b8192", True),
+                                       ("criteo_b1024", True), ("uneven_tables", True)])
+@pytest.mark.parametrize("lean", [False, True])
+def test_unique_row_entries_match_quadruples(name, hint, lean):
+    """sorted_src as 8-byte row entries (CTR_SRC_ROWS) holds, per sorted position, the key
+    and the bag of the quadruple layout's entry, bit for bit, with and without the inverse
+    map, permutation and segment offsets."""
+    ids, kw = UNIQUE_CASES[name]
+    if lean and "offsets" not in kw:
+        pytest.skip("the lean unique rides on bags")
+    say("unique row entries", name, "hint" if hint else "", "lean" if lean else "")
+    n = ids.size
+    got = []
+    for words in (4, 2):
+        src = torch.full((n, words), -7, dtype=torch.int32, device=DEV)
+        if "offsets" in kw:
+            rb = np.zeros(len(kw["rows"]) + 1, dtype=np.int64)
+            rb[1:] = np.cumsum(kw["rows"])
+            res = ctr.ctr_unique_ids(dev(ids), offsets=dev(kw["offsets"]), batch=kw["batch"],
+                                     num_tables=kw["T"], row_base=dev(rb),
+                                     total_rows=int(rb[-1]),
+                                     max_table_rows=max(kw["rows"]) if hint else 0,
+                                     want_perm=not lean, want_seg=not lean,
+                                     want_inverse=not lean, sorted_src=src)
+        else:
+            res = ctr.ctr_unique_ids(dev(ids), key_modulus=kw["modulus"], sorted_src=src)
+        got.append((host(res[0]), int(host(res[2])[0]), host(src)))
+    (u4, U4, q), (u2, U2, r) = got
+    assert U4 == U2
+    np.testing.assert_array_equal(u4[:U4], u2[:U2])
+    assert (q[:, 3] == 0).all()                 # the keys fit 31 bits
+    np.testing.assert_array_equal(r[:, 0], q[:, 2])
+    np.testing.assert_array_equal(r[:, 1], q[:, 1])
+
+
 def test_unique_empty():
     res = ctr.ctr_unique_ids(torch.zeros(0, dtype=torch.int64, device=DEV), key_modulus=10)
     nu, seg = host(res[2]), host(res[4])
@@ -452,6 +489,45 @@ def test_embbag_bwd_matches_oracle(name):
     rg2 = ctr.ctr_embbag_bwd(g_dev[:, 1:, :], (T + 1) * dim, dim, dev(off), B, T, dim, None, None,
                              dev(np.array([U], np.int32)), sorted_src=dev(quads), nnz=len(ids))
     np.testing.assert_array_equal(host(rg2)[:U], got)
+
+
+@pytest.mark.parametrize("gdt", ["f32", "bf16"])
+@pytest.mark.parametrize("tdt", ["f32", "bf16", "f16"])
+@pytest.mark.parametrize("name", BWD_CASES)
+def test_fused_backward_row_entries_match_quadruples(name, tdt, gdt):
+    """ctr_embbag_bwd_sgd through 8-byte (row, bag) entries (CTR_SRC_ROWS: the rows key the
+    segments, uniq is not read) leaves the table bit-identical to the same call through
+    (u, bag, key) quadruples, over hot segments, a segment of 10^6 occurrences (carries over
+    several levels), empty bags and 512-wide rows."""
+    rows, dim, ids, off, B, T = _bwd_case(name)
+    if tdt != "f32" and dim % 8:
+        pytest.skip("16-bit tables take rows of a multiple of 8 values")
+    say("fused bwd row entries", name, tdt, gdt, len(ids))
+    rng = np.random.default_rng(11)
+    dZ = rng.standard_normal((B, T + 1, dim)).astype(np.float32)
+    rb = np.zeros(T + 1, dtype=np.int64)
+    rb[1:] = np.cumsum(rows)
+    keys = orc.form_keys(ids, off, T, B, rb)
+    uniq, inv, perm, _ = orc.unique(keys)
+    n, U = len(ids), uniq.size
+    bag_of = np.searchsorted(off, np.arange(n), side="right") - 1
+    quads = np.zeros((n, 4), dtype=np.int32)
+    quads[:, 0], quads[:, 1] = inv[perm], bag_of[perm]
+    quads[:, 2:] = uniq[inv[perm]].astype(np.int64).view(np.int32).reshape(-1, 2)
+    pairs = np.ascontiguousarray(quads[:, [2, 1]])
+    tt = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}[tdt]
+    gen = torch.Generator(device=DEV).manual_seed(3)
+    t0 = (torch.randn((int(rb[-1]), dim), generator=gen, device=DEV) * 0.1).to(tt)
+    ta, tb = t0.clone(), t0.clone()
+    g = dev(dZ) if gdt == "f32" else dev(dZ).to(torch.bfloat16)
+    nu = dev(np.array([U], np.int32))
+    ctr.ctr_embbag_bwd_sgd(g[:, 1:, :], (T + 1) * dim, dim, dev(off), B, T, n, dev(quads), nu,
+                           ta, dev(uniq), 0.05)
+    ctr.ctr_embbag_bwd_sgd(g[:, 1:, :], (T + 1) * dim, dim, dev(off), B, T, n, dev(pairs), nu,
+                           tb, None, 0.05)
+    torch.cuda.synchronize()
+    assert not torch.equal(ta, t0), "the update changed nothing"
+    assert torch.equal(ta, tb)
 
 
 # ----------------------------------------------------------------------------- SGD
@@ -704,6 +780,48 @@ def test_native_lean_unique_step_matches_full(name, schedule):
         np.testing.assert_array_equal(host(fa.row_grads)[:U], host(fb.row_grads)[:U])
         np.testing.assert_array_equal(host(fa.R), host(fb.R))
         np.testing.assert_array_equal(host(fa.dZ), host(fb.dZ))
+        assert torch.equal(fa.table, fb.table), k
+
+
+@pytest.mark.parametrize("schedule", ["python", "serial", "overlap", "overlap2"])
+@pytest.mark.parametrize("name", ["small_b256", "criteo_b128", "large_t8_b512", "tensornet_b512"])
+def test_row_entry_steps_match_quadruple_steps(name, schedule):
+    """Steps whose unique writes 8-byte row entries for the fused update (the default when no
+    row gradients are kept) leave the table, the distinct rows, R, dZ (or out) bit-identical
+    to steps through (u, bag, key) quadruples; the entries carry the quadruples' key and bag."""
+    w = {"small_b256": lambda: workloads.small(batch=256),
+         "criteo_b128": lambda: workloads.criteo(batch=128),
+         "large_t8_b512": lambda: workloads.large(batch=512, tables=8, rows=400_000),
+         "tensornet_b512": lambda: workloads.tensornet(batch=512, slots=100,
+                                                       table_rows=500_000)}[name]()
+    say("row entry steps", name, schedule)
+    lean = w.interaction
+    pipelined = schedule not in ("python", "serial")
+    fa = FrontEnd(w, DEV, src_rows=False, lean_unique=lean, pipelined=pipelined)
+    fb = FrontEnd(w, DEV, lean_unique=lean, pipelined=pipelined)
+    assert fb.src_rows and fb.sorted_src.shape[1] == 2 and fa.sorted_src.shape[1] == 4
+    if pipelined:
+        fa.native_start(deep=schedule == "overlap2")
+        fb.native_start(deep=schedule == "overlap2")
+    for k in range(3):
+        if schedule == "python":
+            fa.step()
+            fb.step()
+        else:
+            fa.step_native(schedule)
+            fb.step_native(schedule)
+        torch.cuda.synchronize()
+        U = int(host(fa.num_unique)[0])
+        assert U == int(host(fb.num_unique)[0])
+        np.testing.assert_array_equal(host(fa.uniq)[:U], host(fb.uniq)[:U])
+        q, r = host(fa.sorted_src), host(fb.sorted_src)
+        np.testing.assert_array_equal(r[:, 0], q[:, 2])
+        np.testing.assert_array_equal(r[:, 1], q[:, 1])
+        if w.interaction:
+            np.testing.assert_array_equal(host(fa.R), host(fb.R))
+            np.testing.assert_array_equal(host(fa.dZ), host(fb.dZ))
+        else:
+            np.testing.assert_array_equal(host(fa.out), host(fb.out))
         assert torch.equal(fa.table, fb.table), k
 
 

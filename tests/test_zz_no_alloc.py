@@ -22,9 +22,10 @@ def say(*a):
     sys.stdout.flush()
 
 
-def _pair(w, seed, grad_dtype, with_table):
-    """One call of each entry on the same unique, gradients and starting table."""
-    fe = FrontEnd(w, DEV)
+def _pair(w, seed, grad_dtype, with_table, rows=False):
+    """One call of each entry on the same unique, gradients and starting table.  rows: the
+    unique's 8-byte row entries (CTR_SRC_ROWS), which serve the update without row sums."""
+    fe = FrontEnd(w, DEV, src_rows=rows)
     fe.unique()
     B, T, d, n = w.batch, w.num_tables, w.dim, w.nnz
     need = ctr.noalloc_scratch_bytes(n, d)
@@ -39,13 +40,16 @@ def _pair(w, seed, grad_dtype, with_table):
     if with_table:
         ta, tb = fe.table.clone(), fe.table.clone()
         ctr.ctr_embbag_bwd_sgd(g[:, 1:, :], (T + 1) * d, d, fe.offsets, B, T, n, fe.sorted_src,
-                               fe.num_unique, ta, fe.uniq, w.lr, row_grads=ra)
+                               fe.num_unique, ta, fe.uniq, w.lr,
+                               row_grads=None if rows else ra)
         ctr.ctr_embbag_bwd_sgd_noalloc(g[:, 1:, :], (T + 1) * d, d, fe.offsets, B, T, n,
                                        fe.sorted_src, fe.num_unique, tb, fe.uniq, w.lr,
-                                       row_grads=rb)
+                                       row_grads=None if rows else rb)
         torch.cuda.synchronize()
         assert torch.equal(ta, tb), "updated tables differ"
         assert not torch.equal(ta, fe.table), "the update changed nothing"
+        if rows:
+            return
     else:
         ctr.ctr_embbag_bwd(g[:, 1:, :], (T + 1) * d, d, fe.offsets, B, T, d, None, None,
                            fe.num_unique, row_grads=ra, sorted_src=fe.sorted_src, nnz=n)
@@ -63,6 +67,9 @@ def test_noalloc_matches_workspace_entry_on_consecutive_calls():
     _pair(workloads.criteo(batch=1024), 1, torch.bfloat16, True)
     _pair(workloads.small(batch=256), 2, torch.float32, True)
     _pair(workloads.small(batch=64), 3, torch.float32, False)
+    # the same through row entries (no row sums): a bf16 batch, then a smaller fp32 one
+    _pair(workloads.criteo(batch=512), 4, torch.bfloat16, True, rows=True)
+    _pair(workloads.small(batch=128), 5, torch.float32, True, rows=True)
 
 
 def test_noalloc_rejects_a_batch_beyond_its_scratch():
