@@ -930,6 +930,8 @@ def main():
                          else ", forked after the pooling kernel"))
                      if pipelined else "serial: each step dedups its own batch"),
         "ms_per_step_serial": ms_serial if pipelined else ms_step,   # null unless compared
+        "sorted_src": ("8-byte (row, bag) entries (CTR_SRC_ROWS)" if fe.src_rows else
+                       "16-byte (u, bag, key) entries (CTR_SRC_FULL)"),
         "data": "synthetic (seeded; tables from the counter-based fill)",
         "config": {"workload": WORKLOAD_NAMES[args.config] + (
                        "" if args.ids == "zipf" else "; control: uniform IDs, same shapes"),
