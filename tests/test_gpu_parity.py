@@ -825,6 +825,48 @@ def test_row_entry_steps_match_quadruple_steps(name, schedule):
         assert torch.equal(fa.table, fb.table), k
 
 
+@pytest.mark.parametrize("schedule", ["serial", "overlap", "overlap2"])
+@pytest.mark.parametrize("name", ["small_b256", "criteo_b128", "tensornet_b512"])
+def test_row_entry_graph_matches_eager(name, schedule):
+    """The bench's form of the step: native steps through row entries (no row gradients kept,
+    the lean unique for pooled workloads), captured as one HIP graph and replayed twice with
+    unrelated eager work and synchronizations in between, leave the table and the outputs
+    bit-identical to the same steps run eagerly."""
+    w = {"small_b256": lambda: workloads.small(batch=256),
+         "criteo_b128": lambda: workloads.criteo(batch=128),
+         "tensornet_b512": lambda: workloads.tensornet(batch=512, slots=100,
+                                                       table_rows=500_000)}[name]()
+    say("row entry graph", name, schedule)
+    K = 4
+    lean = w.interaction
+    fa = FrontEnd(w, DEV, pipelined=True, lean_unique=lean)
+    fb = FrontEnd(w, DEV, pipelined=True, lean_unique=lean)
+    assert fa.src_rows and fb.src_rows
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(2 * K)]
+    for m in marks:
+        m.record()
+    torch.cuda.synchronize()
+    deep = schedule == "overlap2"
+    g = fb.capture_native(K, schedule, marks)
+    if schedule != "serial":
+        fa.native_start(deep=deep)
+    junk = torch.randn(1 << 20, device=DEV)
+    for _ in range(2):
+        if schedule != "serial":
+            fb.native_start(deep=deep)
+        for _ in range(K):
+            fa.step_native(schedule)
+        g.replay()
+        junk.mul_(1.0001).add_(1.0)
+        torch.cuda.synchronize()
+        assert torch.equal(fa.table, fb.table)
+        if w.interaction:
+            np.testing.assert_array_equal(host(fa.R), host(fb.R))
+            np.testing.assert_array_equal(host(fa.dZ), host(fb.dZ))
+        else:
+            np.testing.assert_array_equal(host(fa.out), host(fb.out))
+
+
 @pytest.mark.parametrize("name", ["small_b256", "criteo_b128", "tensornet_b512"])
 def test_native_deep_schedule_matches_serial(name):
     """ctr_step_run_deep (two batches' uniques in flight, three output sets) leaves the table,
