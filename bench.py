@@ -65,7 +65,7 @@ def grad_elem_bytes(w):
     return 2 if (w.interaction and w.compute == "bf16") else 4
 
 
-def compulsory_bytes(w, U, stage):
+def compulsory_bytes(w, U, stage, z_bytes=4):
     """The stage's bytes with each distinct row read once: the pooled gather reads U rows
     instead of nnz; the fused backward reads each bag's gradient row once (T*B rows, or one
     per occurrence without bags) instead of once per occurrence."""
@@ -77,16 +77,17 @@ def compulsory_bytes(w, U, stage):
     assert stage == "embbag_fwd"
     if w.interaction:
         nb = w.num_tables * w.batch
-        return U * rb + 8 * n + 8 * (nb + 1) + 4 * nb * d
+        return U * rb + 8 * n + 8 * (nb + 1) + z_bytes * nb * d
     return U * 4 * d + 4 * n + 8 * (n + 1) + 4 * n * d
 
 
-def stage_bytes(w, U, src_bytes=16):
+def stage_bytes(w, U, src_bytes=16, z_bytes=4):
     """Algorithmic bytes moved by each stage (what the method must read and write).  The
     fused backward + SGD counts every occurrence's gradient row (at the gradient's element
     size), the occurrence's 8-byte index, and the read and write of each updated row.
     src_bytes: bytes per sorted position of the unique's output for the backward (16 for
-    (u, bag, key) quadruples, 8 for row entries)."""
+    (u, bag, key) quadruples, 8 for row entries).  z_bytes: bytes per value of Z (4, or 2 for
+    a bf16 Z)."""
     n = w.nnz
     d = w.dim
     rb = d * (2 if w.dtype == "bf16" else 4)
@@ -95,10 +96,10 @@ def stage_bytes(w, U, src_bytes=16):
         B, T, F, P = w.batch, w.num_tables, w.F, w.P
         nb = T * B
         return {
-            "embbag_fwd": n * rb + 8 * n + 8 * (nb + 1) + 4 * nb * d,
-            "interaction_fwd": 4 * B * F * d + 4 * B * (d + P),
+            "embbag_fwd": n * rb + 8 * n + 8 * (nb + 1) + z_bytes * nb * d,
+            "interaction_fwd": z_bytes * B * F * d + 4 * B * (d + P),
             # dR and Z read, dZ written at its stored width (bf16 for a bf16 backward)
-            "interaction_bwd": 4 * B * (d + P) + (4 + sg) * B * F * d,
+            "interaction_bwd": 4 * B * (d + P) + (z_bytes + sg) * B * F * d,
             # the pooled step's unique: ids and offsets in; the distinct rows and sorted_src
             # (the backward's input, src_bytes per position) out
             "unique": 8 * n + 8 * (nb + 1) + src_bytes * n + 8 * U,
@@ -238,33 +239,41 @@ def time_variants(fe, w, K: int):
     Pg = F * F
     dRg = torch.randn((B, d + Pg), generator=gen, device="cuda")
     Rg = torch.empty((B, d + Pg), device="cuda")
-    dZ = torch.empty_like(fe.Z)
+    Zf = fe.Z if fe.Z.dtype == torch.float32 else fe.Z.float()   # the fp32-Z entry points'
+    dZ = torch.empty_like(Zf)
     out = torch.empty((B,), device="cuda")
     calls = {
-        "interaction_self_fwd": (ctr.ctr_dot_interaction_self_fwd(fe.Z, fe.compute, R, prepare=True),
+        "interaction_self_fwd": (ctr.ctr_dot_interaction_self_fwd(Zf, fe.compute, R, prepare=True),
                                  4 * B * F * d + 4 * B * (d + P)),
-        "interaction_self_bwd": (ctr.ctr_dot_interaction_self_bwd(fe.Z, dR, fe.compute, dZ,
+        "interaction_self_bwd": (ctr.ctr_dot_interaction_self_bwd(Zf, dR, fe.compute, dZ,
                                                                   prepare=True),
                                  4 * B * (d + P) + 8 * B * F * d),
-        "interaction_gram_fwd": (ctr.ctr_dot_interaction_gram_fwd(fe.Z, fe.compute, Rg,
+        "interaction_gram_fwd": (ctr.ctr_dot_interaction_gram_fwd(Zf, fe.compute, Rg,
                                                                   prepare=True),
                                  4 * B * F * d + 4 * B * (d + Pg)),
-        "interaction_gram_bwd": (ctr.ctr_dot_interaction_gram_bwd(fe.Z, dRg, fe.compute, dZ,
+        "interaction_gram_bwd": (ctr.ctr_dot_interaction_gram_bwd(Zf, dRg, fe.compute, dZ,
                                                                   prepare=True),
                                  4 * B * (d + Pg) + 8 * B * F * d),
-        "fm_fwd": (ctr.ctr_fm_interaction_fwd(fe.Z, out, prepare=True), 4 * B * F * d + 4 * B),
-        "fm_bwd": (ctr.ctr_fm_interaction_bwd(fe.Z, dout, dZ, prepare=True),
+        "fm_fwd": (ctr.ctr_fm_interaction_fwd(Zf, out, prepare=True), 4 * B * F * d + 4 * B),
+        "fm_bwd": (ctr.ctr_fm_interaction_bwd(Zf, dout, dZ, prepare=True),
                    8 * B * F * d + 4 * B),
     }
     Pd = F * (F - 1) // 2                              # the strict pair set of the step
-    pool = stage_bytes(w, 0)["embbag_fwd"]
+    pool = stage_bytes(w, 0)["embbag_fwd"]             # (the fused call's Z is fp32)
     fused = pool + 4 * B * d + 4 * B * (d + Pd)
-    calls["embbag_interaction_fwd"] = (fe._c_embbag_interaction_fwd, fused)
+    fused_call = fe._c_embbag_interaction_fwd
+    if fused_call is None:                             # a bf16 Z: the fused call on a copy
+        fused_call = ctr.ctr_embbag_interaction_fwd(
+            fe.table, fe.indices, fe.offsets, Zf, fe.compute,
+            torch.empty((B, d + Pd), device="cuda"), row_base=fe.row_base, prepare=True)
+    calls["embbag_interaction_fwd"] = (fused_call, fused)
 
     def separate():
         fe._c_embbag_fwd()
         fe._c_interaction_fwd()
-    calls["embbag_fwd+interaction_fwd"] = (separate, fused + 4 * B * F * d)
+    zb = 2 if fe.z_bf16 else 4
+    sep = stage_bytes(w, 0, z_bytes=zb)
+    calls["embbag_fwd+interaction_fwd"] = (separate, sep["embbag_fwd"] + sep["interaction_fwd"])
     res = {}
     for name, (call, nbytes) in calls.items():
         for _ in range(3):
@@ -723,8 +732,9 @@ def main():
         sys.exit(2)
     # the pooled step's unique fills what its backward reads (no inverse map: nothing in the
     # pooled step reads it); the batch-matrix step pools through the inverse map
+    # matrix-core workloads hold Z in bf16: the operands the interaction takes, in half the bytes
     fe = FrontEnd(w, "cuda", pipelined=pipelined, rounding=args.rounding,
-                  lean_unique=w.interaction)
+                  lean_unique=w.interaction, z_bf16=w.interaction and w.compute == "bf16")
     st = fe.stages()
     torch.cuda.synchronize()
     if args.copy_calibration:
@@ -793,7 +803,7 @@ def main():
         stage_ms_cold = {n: sum(a.elapsed_time(b) for a, b in cold[n]) / len(cold[n])
                          for n in names}
         del flush, cold
-    byts = stage_bytes(w, U, 8 if fe.src_rows else 16)
+    byts = stage_bytes(w, U, 8 if fe.src_rows else 16, 2 if fe.z_bf16 else 4)
     # the roofline's kernel: the one that takes the most time per step, among the kernels
     # whose launches the timing marks can bracket (ctr_step_run: the pooling kernel, or the
     # backward's first reduce-by-key level, which carries nearly all of the backward's time)
@@ -896,7 +906,7 @@ def main():
             print("[bench] CPU oracle of the MLPs", file=sys.stderr, flush=True)
             dlrm["cpu_baseline_mlp"] = cpu_baseline_mlp(w, min(args.cpu_seconds, 8.0))
 
-    comp = (compulsory_bytes(w, U, dominant) if dominant in ("embbag_fwd", "embbag_bwd_sgd")
+    comp = (compulsory_bytes(w, U, dominant, 2 if fe.z_bf16 else 4) if dominant in ("embbag_fwd", "embbag_bwd_sgd")
             else None)
     step_bytes = sum(byts[k] for k in stage_ms)          # the stages the step runs
     value = w.nnz / (ms_step * 1e-3)
@@ -930,6 +940,7 @@ def main():
                          else ", forked after the pooling kernel"))
                      if pipelined else "serial: each step dedups its own batch"),
         "ms_per_step_serial": ms_serial if pipelined else ms_step,   # null unless compared
+        "z_dtype": "bf16" if fe.z_bf16 else "f32",
         "sorted_src": ("8-byte (row, bag) entries (CTR_SRC_ROWS)" if fe.src_rows else
                        "16-byte (u, bag, key) entries (CTR_SRC_FULL)"),
         "data": "synthetic (seeded; tables from the counter-based fill)",
@@ -968,7 +979,8 @@ def main():
         "pooling": {"ms": round(stage_ms["embbag_fwd"], 5), "bytes": byts["embbag_fwd"],
                     "frac": byts["embbag_fwd"] / (stage_ms["embbag_fwd"] * 1e-3) / 1e9
                     / HBM_PEAK_GBPS,
-                    "compulsory_frac": compulsory_bytes(w, U, "embbag_fwd")
+                    "compulsory_frac": compulsory_bytes(w, U, "embbag_fwd",
+                                                        2 if fe.z_bf16 else 4)
                     / (stage_ms["embbag_fwd"] * 1e-3) / 1e9 / HBM_PEAK_GBPS},
         # the interaction alone: memory and matrix-core fractions
         "interaction": interaction_block(w, stage_ms, byts) if w.interaction else None,

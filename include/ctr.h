@@ -145,8 +145,11 @@ int32_t ctr_gather_rows(const void* table, int32_t dtype, int64_t total_rows, in
  * For every bag (t, b), t < num_tables, b < batch:
  *   out[b*out_stride_b + t*out_stride_t + c] = sum over k in the bag of
  *       table[(row_base ? row_base[t] : 0) + indices[k], c]       (fp32 accumulation)
- * Duplicates count with multiplicity; an empty bag writes zeros.  out_stride_* are in
- * floats and multiples of 4, so the pooled vectors can go straight into Z[b, 1 + t, :].
+ * Duplicates count with multiplicity; an empty bag writes zeros.  out_dtype: CTR_F32, or
+ * CTR_BF16 (the fp32 sum rounded to nearest-even once, at the store: the operand the
+ * matrix-core interaction takes, in half the bytes).  out is 16-byte aligned; out_stride_* are
+ * in elements and multiples of 4 (fp32) or 8 (bf16), so the pooled vectors can go straight
+ * into Z[b, 1 + t, :].
  * indices: int32 or int64 [nnz]; offsets: int64 [num_tables*batch + 1].
  * A bag's rows are added in occurrence order in pieces of at most a few hundred, and the
  * pieces joined in order, except in a bag of more than 4096 occurrences: that one is summed
@@ -159,8 +162,9 @@ int32_t ctr_embbag_fwd(const void* table, int32_t dtype, int64_t total_rows, int
                        const int64_t* row_base, int32_t num_tables,
                        const void* indices, int32_t index_type, int64_t nnz,
                        const int64_t* offsets, int64_t batch,
-                       float* out, int64_t out_stride_b, int64_t out_stride_t,
-                       void* workspace, size_t* workspace_bytes, void* stream);
+                       void* out, int32_t out_dtype, int64_t out_stride_b,
+                       int64_t out_stride_t, void* workspace, size_t* workspace_bytes,
+                       void* stream);
 
 /*
  * ctr_embbag_bwd -- chain rule of the sum pooling, reduced per distinct row ([TN]
@@ -277,9 +281,13 @@ uint64_t ctr_sr_step_seed(uint64_t base, int64_t k);
  *   R[b*r_stride + dim + i*(i-1)/2 + j]    = <Z[b, i, :], Z[b, j, :]>   F > i > j >= 0
  * compute = CTR_F32: fp32 arithmetic.  compute = CTR_BF16: operands rounded to bf16
  * (nearest-even) on matrix cores, fp32 accumulation (dim a multiple of 16, F <= 128).
+ * z_dtype: CTR_F32, or CTR_BF16 with compute = CTR_BF16 (Z held in bf16, as ctr_embbag_fwd
+ * writes it with out_dtype CTR_BF16: the same operands in half the bytes; the dense
+ * passthrough is then the bf16 vector, widened exactly).  Z 16-byte aligned for bf16 compute.
  */
-int32_t ctr_dot_interaction_fwd(const float* Z, int64_t batch, int32_t num_vectors, int32_t dim,
-                                int32_t compute, float* R, int64_t r_stride, void* stream);
+int32_t ctr_dot_interaction_fwd(const void* Z, int32_t z_dtype, int64_t batch,
+                                int32_t num_vectors, int32_t dim, int32_t compute, float* R,
+                                int64_t r_stride, void* stream);
 
 /*
  * ctr_embbag_interaction_fwd -- the pooling of ctr_embbag_fwd ([DHEN] 2.1) and the dot
@@ -314,9 +322,11 @@ int32_t ctr_embbag_interaction_fwd(const void* table, int32_t dtype, int64_t tot
  * needs compute = CTR_BF16).  A bf16 dZ halves the bytes the backward of the pooling re-reads
  * per occurrence; its consumer accumulates in fp32 (ctr_embbag_bwd_sgd with grad_dtype =
  * CTR_BF16).  compute as in the forward (bf16 rounds dP and Z; Z and dZ 16-byte aligned).
+ * z_dtype as in the forward; a bf16 Z takes a bf16 dZ.
  */
-int32_t ctr_dot_interaction_bwd(const float* Z, const float* dR, int64_t dr_stride,
-                                int64_t batch, int32_t num_vectors, int32_t dim,
+int32_t ctr_dot_interaction_bwd(const void* Z, int32_t z_dtype, const float* dR,
+                                int64_t dr_stride, int64_t batch, int32_t num_vectors,
+                                int32_t dim,
                                 int32_t compute, int32_t dz_dtype, void* dZ, void* stream);
 
 /*
@@ -450,6 +460,10 @@ int32_t ctr_validate_csr(const void* indices, int32_t index_type, int64_t nnz,
  *     -> ctr_embbag_bwd_sgd over dout (SGD on the touched table rows).
  *     E, out, dout: fp32 [nnz, dim].
  *
+ * z_dtype (pooled step): the element type of Z, CTR_F32, or CTR_BF16 with compute = CTR_BF16
+ * and grad_dtype = CTR_BF16 (the pooling writes bf16 vectors, the interaction reads them; the
+ * dense vector Z[:, 0, :] is then bf16 too).
+ *
  * Unique outputs exist in CTR_STEP_SETS = 3 sets: the serial schedule uses set 0, the
  * pipelined schedules of ctr_step_run sets 0 and 1, ctr_step_run_deep all three (an unused
  * set may repeat set 0).  Each array has capacity nnz
@@ -487,7 +501,7 @@ typedef struct {
   int32_t compute;                /* interaction arithmetic, CTR_F32 or CTR_BF16 */
   int64_t total_rows;
   float lr;
-  float* Z;
+  void* Z;                        /* z_dtype elements */
   float* R;
   const float* dR;
   void* dZ;                       /* fp32 or bf16, see grad_dtype */
@@ -521,6 +535,7 @@ typedef struct {
   size_t ws_pool_bytes;
   int32_t src_layout;             /* sorted_src's layout, CTR_SRC_FULL or CTR_SRC_ROWS (the
                                      latter needs row_grads NULL) */
+  int32_t z_dtype;                /* pooled step: Z's element type, CTR_F32 or CTR_BF16 */
 } ctr_step_t;
 
 /*

@@ -192,10 +192,12 @@ int32_t ctr_gather_rows(const void* table, int32_t dtype, int64_t total_rows, in
 int32_t ctr_embbag_fwd(const void* table, int32_t dtype, int64_t total_rows, int32_t dim,
                        const int64_t* row_base, int32_t num_tables, const void* indices,
                        int32_t index_type, int64_t nnz, const int64_t* offsets, int64_t batch,
-                       float* out, int64_t out_stride_b, int64_t out_stride_t, void* workspace,
-                       size_t* workspace_bytes, void* stream) {
+                       void* out, int32_t out_dtype, int64_t out_stride_b, int64_t out_stride_t,
+                       void* workspace, size_t* workspace_bytes, void* stream) {
   g_msg[0] = 0;
   if (!workspace_bytes) return fail(CTR_ERR_INVALID_ARGUMENT, "workspace_bytes is NULL");
+  if (out_dtype != CTR_F32 && out_dtype != CTR_BF16)
+    return fail(CTR_ERR_INVALID_ARGUMENT, "out_dtype %d is not CTR_F32 or CTR_BF16", out_dtype);
   if (nnz < 0 || nnz > kMaxElems) return fail(CTR_ERR_INVALID_ARGUMENT, "bad nnz");
   if (dim <= 0 || dim > 4096) return fail(CTR_ERR_INVALID_ARGUMENT, "bad dim %d", dim);
   const size_t need = ctr::embbag_fwd_workspace_bytes(nnz, dim);
@@ -220,12 +222,16 @@ int32_t ctr_embbag_fwd(const void* table, int32_t dtype, int64_t total_rows, int
     return fail(CTR_ERR_INVALID_ARGUMENT, "negative output stride");
   if (num_tables > 1 && out_stride_t < dim && out_stride_b < dim)
     return fail(CTR_ERR_INVALID_ARGUMENT, "output strides smaller than dim");
-  if (!aligned16(out) || out_stride_b % 4 || out_stride_t % 4)
-    return fail(CTR_ERR_UNSUPPORTED, "out must be 16-byte aligned with strides multiple of 4");
+  // fp32 vectors go out in 16-byte pieces of 4 values, bf16 ones in pieces of up to 8
+  const int64_t sm = out_dtype == CTR_BF16 ? 8 : 4;
+  if (!aligned16(out) || out_stride_b % sm || out_stride_t % sm)
+    return fail(CTR_ERR_UNSUPPORTED, "out must be 16-byte aligned with strides multiple of %d",
+                (int)sm);
   return hip_status(ctr::launch_embbag_fwd(table, dtype, total_rows, dim, row_base,
                                            num_tables, indices, index_type == CTR_I64, nnz,
-                                           offsets, batch, out, out_stride_b, out_stride_t,
-                                           workspace, (hipStream_t)stream),
+                                           offsets, batch, out, out_dtype == CTR_BF16,
+                                           out_stride_b, out_stride_t, workspace,
+                                           (hipStream_t)stream),
                     "ctr_embbag_fwd");
 }
 
@@ -521,43 +527,62 @@ static int32_t check_interaction(const float* Z, int64_t batch, int32_t F, int32
   return CTR_OK;
 }
 
-static int32_t interaction_fwd_common(const float* Z, int64_t batch, int32_t F, int32_t dim,
-                                      int32_t compute, int pairs, float* R, int64_t r_stride,
-                                      void* stream, const char* name) {
+// A bf16 Z (z_dtype CTR_BF16): the matrix-core interaction of the strict pairs only.
+static int32_t check_z_dtype(int32_t z_dtype, int32_t compute, int pairs) {
+  if (z_dtype != CTR_F32 && z_dtype != CTR_BF16)
+    return fail(CTR_ERR_INVALID_ARGUMENT, "z_dtype %d is not CTR_F32 or CTR_BF16", z_dtype);
+  if (z_dtype == CTR_BF16 && (compute != CTR_BF16 || pairs != ctr::kPairStrict))
+    return fail(CTR_ERR_UNSUPPORTED,
+                "a bf16 Z needs compute = CTR_BF16 (the dot interaction on matrix cores)");
+  return CTR_OK;
+}
+
+static int32_t interaction_fwd_common(const void* Z, int32_t z_dtype, int64_t batch, int32_t F,
+                                      int32_t dim, int32_t compute, int pairs, float* R,
+                                      int64_t r_stride, void* stream, const char* name) {
   g_msg[0] = 0;
-  int32_t st = check_interaction(Z, batch, F, dim, compute, pairs, R, r_stride);
+  int32_t st = check_z_dtype(z_dtype, compute, pairs);
   if (st) return st;
-  return hip_status(ctr::launch_interaction_fwd(Z, batch, F, dim, compute == CTR_BF16, pairs, R,
-                                                r_stride, (hipStream_t)stream),
+  st = check_interaction(static_cast<const float*>(Z), batch, F, dim, compute, pairs, R,
+                         r_stride);
+  if (st) return st;
+  return hip_status(ctr::launch_interaction_fwd(Z, z_dtype == CTR_BF16, batch, F, dim,
+                                                compute == CTR_BF16, pairs, R, r_stride,
+                                                (hipStream_t)stream),
                     name);
 }
 
-static int32_t interaction_bwd_common(const float* Z, const float* dR, int64_t dr_stride,
-                                      int64_t batch, int32_t F, int32_t dim, int32_t compute,
-                                      int pairs, int32_t dz_dtype, void* dZ, void* stream,
-                                      const char* name) {
+static int32_t interaction_bwd_common(const void* Z, int32_t z_dtype, const float* dR,
+                                      int64_t dr_stride, int64_t batch, int32_t F, int32_t dim,
+                                      int32_t compute, int pairs, int32_t dz_dtype, void* dZ,
+                                      void* stream, const char* name) {
   g_msg[0] = 0;
   if (dz_dtype != CTR_F32 && dz_dtype != CTR_BF16)
     return fail(CTR_ERR_INVALID_ARGUMENT, "dz_dtype %d is not CTR_F32 or CTR_BF16", dz_dtype);
   const bool dz_bf16 = dz_dtype == CTR_BF16;
-  int32_t st = check_interaction(Z, batch, F, dim, compute, pairs, static_cast<const float*>(dZ),
-                                 dr_stride);
+  int32_t st = check_z_dtype(z_dtype, compute, pairs);
+  if (st) return st;
+  if (z_dtype == CTR_BF16 && !dz_bf16)
+    return fail(CTR_ERR_UNSUPPORTED, "a bf16 Z takes a bf16 dZ");
+  st = check_interaction(static_cast<const float*>(Z), batch, F, dim, compute, pairs,
+                         static_cast<const float*>(dZ), dr_stride);
   if (st) return st;
   if (batch > 0 && !dR) return fail(CTR_ERR_INVALID_ARGUMENT, "dR is NULL");
   if (dz_bf16 && compute != CTR_BF16)
     return fail(CTR_ERR_UNSUPPORTED, "a bf16 dZ needs compute = CTR_BF16");
   if (compute == CTR_BF16 && dZ && !aligned16(dZ))
     return fail(CTR_ERR_UNSUPPORTED, "dZ is not 16-byte aligned");
-  return hip_status(ctr::launch_interaction_bwd(Z, dR, dr_stride, batch, F, dim,
-                                                compute == CTR_BF16, pairs, dz_bf16, dZ,
+  return hip_status(ctr::launch_interaction_bwd(Z, z_dtype == CTR_BF16, dR, dr_stride, batch, F,
+                                                dim, compute == CTR_BF16, pairs, dz_bf16, dZ,
                                                 (hipStream_t)stream),
                     name);
 }
 
-int32_t ctr_dot_interaction_fwd(const float* Z, int64_t batch, int32_t num_vectors, int32_t dim,
-                                int32_t compute, float* R, int64_t r_stride, void* stream) {
-  return interaction_fwd_common(Z, batch, num_vectors, dim, compute, ctr::kPairStrict, R,
-                                r_stride, stream, "ctr_dot_interaction_fwd");
+int32_t ctr_dot_interaction_fwd(const void* Z, int32_t z_dtype, int64_t batch,
+                                int32_t num_vectors, int32_t dim, int32_t compute, float* R,
+                                int64_t r_stride, void* stream) {
+  return interaction_fwd_common(Z, z_dtype, batch, num_vectors, dim, compute, ctr::kPairStrict,
+                                R, r_stride, stream, "ctr_dot_interaction_fwd");
 }
 
 int32_t ctr_embbag_interaction_fwd(const void* table, int32_t dtype, int64_t total_rows,
@@ -599,24 +624,25 @@ int32_t ctr_embbag_interaction_fwd(const void* table, int32_t dtype, int64_t tot
                     "ctr_embbag_interaction_fwd");
 }
 
-int32_t ctr_dot_interaction_bwd(const float* Z, const float* dR, int64_t dr_stride,
-                                int64_t batch, int32_t num_vectors, int32_t dim, int32_t compute,
-                                int32_t dz_dtype, void* dZ, void* stream) {
-  return interaction_bwd_common(Z, dR, dr_stride, batch, num_vectors, dim, compute,
+int32_t ctr_dot_interaction_bwd(const void* Z, int32_t z_dtype, const float* dR,
+                                int64_t dr_stride, int64_t batch, int32_t num_vectors,
+                                int32_t dim, int32_t compute, int32_t dz_dtype, void* dZ,
+                                void* stream) {
+  return interaction_bwd_common(Z, z_dtype, dR, dr_stride, batch, num_vectors, dim, compute,
                                 ctr::kPairStrict, dz_dtype, dZ, stream, "ctr_dot_interaction_bwd");
 }
 
 int32_t ctr_dot_interaction_self_fwd(const float* Z, int64_t batch, int32_t num_vectors,
                                      int32_t dim, int32_t compute, float* R, int64_t r_stride,
                                      void* stream) {
-  return interaction_fwd_common(Z, batch, num_vectors, dim, compute, ctr::kPairSelf, R,
+  return interaction_fwd_common(Z, CTR_F32, batch, num_vectors, dim, compute, ctr::kPairSelf, R,
                                 r_stride, stream, "ctr_dot_interaction_self_fwd");
 }
 
 int32_t ctr_dot_interaction_self_bwd(const float* Z, const float* dR, int64_t dr_stride,
                                      int64_t batch, int32_t num_vectors, int32_t dim,
                                      int32_t compute, int32_t dz_dtype, void* dZ, void* stream) {
-  return interaction_bwd_common(Z, dR, dr_stride, batch, num_vectors, dim, compute,
+  return interaction_bwd_common(Z, CTR_F32, dR, dr_stride, batch, num_vectors, dim, compute,
                                 ctr::kPairSelf, dz_dtype, dZ, stream,
                                 "ctr_dot_interaction_self_bwd");
 }
@@ -624,14 +650,14 @@ int32_t ctr_dot_interaction_self_bwd(const float* Z, const float* dR, int64_t dr
 int32_t ctr_dot_interaction_gram_fwd(const float* Z, int64_t batch, int32_t num_vectors,
                                      int32_t dim, int32_t compute, float* R, int64_t r_stride,
                                      void* stream) {
-  return interaction_fwd_common(Z, batch, num_vectors, dim, compute, ctr::kPairGram, R,
+  return interaction_fwd_common(Z, CTR_F32, batch, num_vectors, dim, compute, ctr::kPairGram, R,
                                 r_stride, stream, "ctr_dot_interaction_gram_fwd");
 }
 
 int32_t ctr_dot_interaction_gram_bwd(const float* Z, const float* dR, int64_t dr_stride,
                                      int64_t batch, int32_t num_vectors, int32_t dim,
                                      int32_t compute, int32_t dz_dtype, void* dZ, void* stream) {
-  return interaction_bwd_common(Z, dR, dr_stride, batch, num_vectors, dim, compute,
+  return interaction_bwd_common(Z, CTR_F32, dR, dr_stride, batch, num_vectors, dim, compute,
                                 ctr::kPairGram, dz_dtype, dZ, stream,
                                 "ctr_dot_interaction_gram_bwd");
 }

@@ -29,7 +29,7 @@ size_t embbag_fwd_workspace_bytes(int64_t nnz, int dim);
 hipError_t launch_embbag_fwd(const void* table, int elt, int64_t total_rows, int dim,
                              const int64_t* row_base, int32_t num_tables, const void* idx,
                              bool idx64, int64_t nnz, const int64_t* offsets, int64_t batch,
-                             float* out, int64_t sb, int64_t st, void* workspace,
+                             void* out, bool out_bf16, int64_t sb, int64_t st, void* workspace,
                              hipStream_t s);
 hipError_t launch_gather_rows(const void* table, int elt, int64_t total_rows, int dim,
                               const int64_t* rows, const int32_t* num_rows, int64_t capacity,
@@ -95,11 +95,14 @@ hipError_t launch_dict_pool(const int64_t* values, int64_t nnz, const int64_t* o
 constexpr int kPairStrict = 0, kPairSelf = 1, kPairGram = 2;
 bool interaction_bf16_supported(int F, int dim, int pairs);
 bool interaction_f32_supported(int F, int dim, int pairs);
-hipError_t launch_interaction_fwd(const float* Z, int64_t batch, int F, int dim, bool bf16,
-                                  int pairs, float* R, int64_t r_stride, hipStream_t s);
-hipError_t launch_interaction_bwd(const float* Z, const float* dR, int64_t dr_stride,
-                                  int64_t batch, int F, int dim, bool bf16, int pairs,
-                                  bool out_bf16, void* dZ, hipStream_t s);
+// z_bf16: Z held in bf16 (strict pairs on matrix cores, and a bf16 dZ in the backward;
+// anything else returns hipErrorInvalidValue); otherwise fp32.
+hipError_t launch_interaction_fwd(const void* Z, bool z_bf16, int64_t batch, int F, int dim,
+                                  bool bf16, int pairs, float* R, int64_t r_stride,
+                                  hipStream_t s);
+hipError_t launch_interaction_bwd(const void* Z, bool z_bf16, const float* dR,
+                                  int64_t dr_stride, int64_t batch, int F, int dim, bool bf16,
+                                  int pairs, bool out_bf16, void* dZ, hipStream_t s);
 hipError_t launch_fm_fwd(const float* Z, int64_t batch, int F, int dim, float* out,
                          hipStream_t s);
 hipError_t launch_fm_bwd(const float* Z, const float* dout, int64_t batch, int F, int dim,

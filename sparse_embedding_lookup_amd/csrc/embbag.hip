@@ -35,6 +35,42 @@ __device__ __forceinline__ void accumulate(float* acc, const uint4& x) {
   }
 }
 
+// Where the pooled vectors go: element b*sb + t*st + c of `p`, fp32, or bf16 rounded to
+// nearest-even once at the store (the sums stay fp32 until then); strides in elements.
+struct PoolOut {
+  void* p;
+  int64_t sb, st;
+  bool bf16;
+  __device__ __forceinline__ int64_t at(int64_t b, int64_t t) const { return b * sb + t * st; }
+};
+
+// N (1, 4 or 8) consecutive values of a pooled vector at element offset `off`: one 4-, 16- or
+// 32-byte fp32 store, or a 2-, 8- or 16-byte bf16 one.
+template <int N>
+__device__ __forceinline__ void store_pooled(const PoolOut& o, int64_t off, const float* v) {
+  if (o.bf16) {
+    uint16_t* q = static_cast<uint16_t*>(o.p) + off;
+    if constexpr (N == 1) {
+      *q = (uint16_t)f32_to_bf16_bits(v[0]);
+    } else {
+      uint32_t w[N / 2];
+#pragma unroll
+      for (int i = 0; i < N / 2; ++i)
+        w[i] = f32_to_bf16_bits(v[2 * i]) | (f32_to_bf16_bits(v[2 * i + 1]) << 16);
+      if constexpr (N == 4) *reinterpret_cast<uint2*>(q) = make_uint2(w[0], w[1]);
+      else *reinterpret_cast<uint4*>(q) = make_uint4(w[0], w[1], w[2], w[3]);
+    }
+  } else {
+    float* q = static_cast<float*>(o.p) + off;
+    if constexpr (N == 1) {
+      *q = v[0];
+    } else {
+      reinterpret_cast<float4*>(q)[0] = make_float4(v[0], v[1], v[2], v[3]);
+      if constexpr (N == 8) reinterpret_cast<float4*>(q)[1] = make_float4(v[4], v[5], v[6], v[7]);
+    }
+  }
+}
+
 constexpr int kMaxBagsPerGroup = 16;
 
 // A bag of more than kLongBag occurrences is not pooled by the kernels below (they skip its
@@ -56,7 +92,7 @@ __global__ __launch_bounds__(kThreads) void embbag_fwd_kernel(
     const char* __restrict__ table, int64_t total_rows, int64_t row_bytes, int vecs,
     const int64_t* __restrict__ row_base, const TIdx* __restrict__ idx, int64_t nnz,
     const int64_t* __restrict__ offsets, int64_t batch, int64_t num_bags, int nbg,
-    float* __restrict__ out, int64_t sb, int64_t st, int32_t* __restrict__ long_flag) {
+    PoolOut out, int32_t* __restrict__ long_flag) {
   constexpr int E = TY != kEltF32 ? 8 : 4;
   constexpr int kGroups = kThreads / G;
   constexpr int kU = (VPL == 1 && G <= 8) ? 16 : 8;   // rows in flight per group
@@ -89,16 +125,12 @@ __global__ __launch_bounds__(kThreads) void embbag_fwd_kernel(
   auto flush = [&](int j) {                    // a long bag is written by its own kernels
     const int64_t s = s0 + j;
     const int64_t t = s / batch, b = s - t * batch;
-    float* o = out + b * sb + t * st;
+    const int64_t o = out.at(b, t);
     const bool keep = !(any_long && is_long(j));
 #pragma unroll
     for (int a = 0; a < VPL; ++a) {
       const int vi = a * G + lane;
-      if (keep && vi < vecs) {
-        float4* p = reinterpret_cast<float4*>(o + (int64_t)vi * E);
-        p[0] = make_float4(acc[a][0], acc[a][1], acc[a][2], acc[a][3]);
-        if (E == 8) p[1] = make_float4(acc[a][4 % E], acc[a][5 % E], acc[a][6 % E], acc[a][7 % E]);
-      }
+      if (keep && vi < vecs) store_pooled<E>(out, o + (int64_t)vi * E, acc[a]);
 #pragma unroll
       for (int e = 0; e < E; ++e) acc[a][e] = 0.f;
     }
@@ -184,7 +216,7 @@ __device__ __forceinline__ void pool_block(
     int64_t blk, const char* __restrict__ table, int64_t total_rows, int64_t row_bytes,
     int vecs, const int64_t* __restrict__ row_base, const TIdx* __restrict__ idx, int64_t nnz,
     const int64_t* __restrict__ offsets, int64_t batch, int64_t num_bags, int nbb,
-    float* __restrict__ out, int64_t sb, int64_t st, int32_t* __restrict__ long_flag) {
+    PoolOut out, int32_t* __restrict__ long_flag) {
   constexpr int E = TY != kEltF32 ? 8 : 4;
   constexpr int kGroups = kThreads / G;
   constexpr int kU = (VPL == 1 && G <= 8) ? 16 : 8;   // rows in flight per group
@@ -205,20 +237,16 @@ __device__ __forceinline__ void pool_block(
   __syncthreads();
   if (nb == 0) return;
   auto base_of = [&](int c) -> int64_t { return s_base[c]; };
-  auto out_row = [&](int c) -> float* {
+  auto out_row = [&](int c) -> int64_t {
     const int64_t sg = s0 + c;
     const int64_t t = sg / batch, b = sg - t * batch;
-    return out + b * sb + t * st;
+    return out.at(b, t);
   };
-  auto store = [&](float* o, const float (&acc)[VPL][E]) {
+  auto store = [&](int64_t o, const float (&acc)[VPL][E]) {
 #pragma unroll
     for (int a = 0; a < VPL; ++a) {
       const int vi = a * G + lane;
-      if (vi < vecs) {
-        float4* p = reinterpret_cast<float4*>(o + (int64_t)vi * E);
-        p[0] = make_float4(acc[a][0], acc[a][1], acc[a][2], acc[a][3]);
-        if (E == 8) p[1] = make_float4(acc[a][4 % E], acc[a][5 % E], acc[a][6 % E], acc[a][7 % E]);
-      }
+      if (vi < vecs) store_pooled<E>(out, o + (int64_t)vi * E, acc[a]);
     }
   };
   auto to_lds = [&](float* dst, const float (&acc)[VPL][E]) {
@@ -366,9 +394,9 @@ __device__ __forceinline__ void pool_block(
   // empty bags
   for (int j = threadIdx.x; j < nb; j += kThreads) {
     if (s_off[j] == s_off[j + 1]) {
-      float* o = out_row(j);
-      for (int c2 = 0; c2 < vecs * E; c2 += 4)
-        *reinterpret_cast<float4*>(o + c2) = make_float4(0.f, 0.f, 0.f, 0.f);
+      const int64_t o = out_row(j);
+      const float zero[4] = {0.f, 0.f, 0.f, 0.f};
+      for (int c2 = 0; c2 < vecs * E; c2 += 4) store_pooled<4>(out, o + c2, zero);
     }
   }
 }
@@ -378,10 +406,9 @@ __global__ __launch_bounds__(kThreads) void embbag_fwd_balanced_kernel(
     const char* __restrict__ table, int64_t total_rows, int64_t row_bytes, int vecs,
     const int64_t* __restrict__ row_base, const TIdx* __restrict__ idx, int64_t nnz,
     const int64_t* __restrict__ offsets, int64_t batch, int64_t num_bags, int nbb,
-    float* __restrict__ out, int64_t sb, int64_t st, int32_t* __restrict__ long_flag) {
+    PoolOut out, int32_t* __restrict__ long_flag) {
   pool_block<TIdx, TY, G, VPL, false>(blockIdx.x, table, total_rows, row_bytes, vecs, row_base,
-                                      idx, nnz, offsets, batch, num_bags, nbb, out, sb, st,
-                                      long_flag);
+                                      idx, nnz, offsets, batch, num_bags, nbb, out, long_flag);
 }
 
 // ----------------------------------------------------------------------------- long bags
@@ -410,7 +437,7 @@ __global__ __launch_bounds__(kThreads) void long_bag_kernel(
     const char* __restrict__ table, int64_t total_rows, int64_t row_bytes, int vecs,
     const int64_t* __restrict__ row_base, const TIdx* __restrict__ idx, int64_t nnz,
     const int64_t* __restrict__ offsets, int64_t batch, int64_t num_bags, int nbb,
-    float* __restrict__ out, int64_t sb, int64_t st, int32_t* __restrict__ long_flag,
+    PoolOut out, int32_t* __restrict__ long_flag,
     int64_t* __restrict__ starts, float* __restrict__ partials) {
   constexpr int E = TY != kEltF32 ? 8 : 4;
   constexpr int kGroups = kThreads / G;
@@ -432,8 +459,8 @@ __global__ __launch_bounds__(kThreads) void long_bag_kernel(
       for (int64_t blk = blockIdx.x; blk < nblocks; blk += gridDim.x) {
         __syncthreads();                       // the previous block is done with the LDS
         pool_block<TIdx, TY, G, VPL, true>(blk, table, total_rows, row_bytes, vecs, row_base,
-                                           idx, nnz, offsets, batch, num_bags, nbb, out, sb,
-                                           st, long_flag);
+                                           idx, nnz, offsets, batch, num_bags, nbb, out,
+                                           long_flag);
       }
     }
   }
@@ -536,7 +563,7 @@ __global__ __launch_bounds__(kThreads) void long_bag_kernel(
 __global__ __launch_bounds__(kThreads) void long_bag_combine_kernel(
     const int64_t* __restrict__ offsets, int64_t nnz, int64_t batch, int64_t num_bags,
     int32_t* __restrict__ long_flag, const int64_t* __restrict__ starts,
-    float* __restrict__ partials, int dim, float* __restrict__ out, int64_t sb, int64_t st) {
+    float* __restrict__ partials, int dim, PoolOut out) {
   if (blockIdx.x == 0 && threadIdx.x == 0) *long_flag = 0;
   const int64_t chunks = (nnz + kLongChunk - 1) / kLongChunk;
   for (int64_t k = blockIdx.x; k < chunks; k += gridDim.x) {
@@ -560,9 +587,9 @@ __global__ __launch_bounds__(kThreads) void long_bag_combine_kernel(
     __syncthreads();
   }
   const int64_t t = j / batch, b = j - t * batch;
-  float* o = out + b * sb + t * st;
+  const int64_t o = out.at(b, t);
   const float* r = slot(0);
-  for (int c = threadIdx.x; c < dim; c += kThreads) o[c] = r[c];
+  for (int c = threadIdx.x; c < dim; c += kThreads) store_pooled<1>(out, o + c, r + c);
   __syncthreads();                             // before the next bag's tree
   }
 }
@@ -755,8 +782,9 @@ size_t embbag_fwd_workspace_bytes(int64_t nnz, int dim) {
 hipError_t launch_embbag_fwd(const void* table, int elt, int64_t total_rows, int dim,
                              const int64_t* row_base, int32_t num_tables, const void* idx,
                              bool idx64, int64_t nnz, const int64_t* offsets, int64_t batch,
-                             float* out, int64_t sb, int64_t st, void* workspace,
+                             void* out, bool out_bf16, int64_t sb, int64_t st, void* workspace,
                              hipStream_t s) {
+  const PoolOut po{out, sb, st, out_bf16};
   const int E = elt != kEltF32 ? 8 : 4;
   const int vecs = dim / E;
   const RowGeom rg = row_geom(vecs);
@@ -773,11 +801,11 @@ hipError_t launch_embbag_fwd(const void* table, int elt, int64_t total_rows, int
       if (idx64)                                                                              \
         KERNEL<int64_t, TY, G, VPL><<<(unsigned)(BLOCKS), kThreads, 0, s>>>(                  \
             tb, total_rows, row_bytes, vecs, row_base, (const int64_t*)idx, nnz, offsets,     \
-            batch, num_bags, PER, out, sb, st, long_flag);                                    \
+            batch, num_bags, PER, po, long_flag);                                            \
       else                                                                                    \
         KERNEL<int32_t, TY, G, VPL><<<(unsigned)(BLOCKS), kThreads, 0, s>>>(                  \
             tb, total_rows, row_bytes, vecs, row_base, (const int32_t*)idx, nnz, offsets,     \
-            batch, num_bags, PER, out, sb, st, long_flag);                                    \
+            batch, num_bags, PER, po, long_flag);                                            \
     });                                                                                       \
   } while (0)
   int nbb_used = 0;                               // bags per block of the balanced kernel
@@ -820,15 +848,15 @@ hipError_t launch_embbag_fwd(const void* table, int elt, int64_t total_rows, int
       if (idx64)
         long_bag_kernel<int64_t, TY, G, VPL><<<lgrid, kThreads, 0, s>>>(
             tb, total_rows, row_bytes, vecs, row_base, (const int64_t*)idx, nnz, offsets,
-            batch, num_bags, nbb_used, out, sb, st, long_flag, starts, partials);
+            batch, num_bags, nbb_used, po, long_flag, starts, partials);
       else
         long_bag_kernel<int32_t, TY, G, VPL><<<lgrid, kThreads, 0, s>>>(
             tb, total_rows, row_bytes, vecs, row_base, (const int32_t*)idx, nnz, offsets,
-            batch, num_bags, nbb_used, out, sb, st, long_flag, starts, partials);
+            batch, num_bags, nbb_used, po, long_flag, starts, partials);
     });
   });
   long_bag_combine_kernel<<<lgrid, kThreads, 0, s>>>(offsets, nnz, batch, num_bags, long_flag,
-                                                     starts, partials, dim, out, sb, st);
+                                                     starts, partials, dim, po);
   return hipGetLastError();
 }
 

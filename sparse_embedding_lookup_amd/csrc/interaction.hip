@@ -373,16 +373,26 @@ bool lanes_shape(int F, int dim, int pairs) {
 
 // ------------------------------------------------------------------------- bf16 forward
 // Operand fragment of row-block I, k-step s: lane holds row 32*I + rl, columns
-// 16*s + 8*kg .. +8 of Z[b], rounded to bf16 (rows >= F are zero).
-template <int KS>
-__device__ __forceinline__ void load_row_block(const float* __restrict__ zb, int F, int I,
+// 16*s + 8*kg .. +8 of Z[b], rounded to bf16 (rows >= F are zero).  ZB: Z is held in bf16
+// already (rounded the same way when it was stored): the fragment is one 16-byte load.
+template <int KS, bool ZB>
+__device__ __forceinline__ void load_row_block(const void* __restrict__ zbv, int F, int I,
                                                int rl, int kg, bf16x8* fr) {
   constexpr int dim = KS * 16;
   const int row = 32 * I + rl;
+  const float* zb = static_cast<const float*>(zbv);
 #pragma unroll
   for (int s = 0; s < KS; ++s) {
     float x[8];
-    if (row < F) {
+    if constexpr (ZB) {
+      if (row < F) {
+        fr[s] = *reinterpret_cast<const bf16x8*>(static_cast<const __bf16*>(zbv) + row * dim +
+                                                 16 * s + 8 * kg);
+        continue;
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] = 0.f;
+    } else if (row < F) {
       const float4* p = reinterpret_cast<const float4*>(zb + row * dim + 16 * s + 8 * kg);
       const float4 a = p[0], c = p[1];
       x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
@@ -397,24 +407,28 @@ __device__ __forceinline__ void load_row_block(const float* __restrict__ zb, int
 
 // FB: 32-row blocks covering F (F <= 32*FB); KS: dim / 16 (k-steps of 16).  All FB row
 // blocks of fragments stay in registers.
-template <int FB, int KS, int PS>
+// ZB: Z in bf16 (the dense passthrough is then the bf16 vector, widened exactly).
+template <int FB, int KS, int PS, bool ZB>
 __global__ __launch_bounds__(kThreads) void interaction_fwd_mfma_kernel(
-    const float* __restrict__ Z, int64_t batch, int F, float* __restrict__ R, int64_t r_stride) {
+    const void* __restrict__ Z, int64_t batch, int F, float* __restrict__ R, int64_t r_stride) {
   constexpr int dim = KS * 16;
   const int lane = threadIdx.x & 63;
   const int64_t b = (int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
   if (b >= batch) return;
-  const float* zb = Z + b * (int64_t)F * dim;
+  const int64_t zo = b * (int64_t)F * dim;
+  const void* zb = ZB ? static_cast<const void*>(static_cast<const __bf16*>(Z) + zo)
+                      : static_cast<const void*>(static_cast<const float*>(Z) + zo);
   float* rb = R + b * r_stride;
   const int rl = lane & 31, kg = lane >> 5;
-  for (int c = lane; c < dim; c += 64) rb[c] = zb[c];   // dense passthrough (exact)
+  for (int c = lane; c < dim; c += 64)                  // dense passthrough (exact)
+    rb[c] = ZB ? (float)static_cast<const __bf16*>(zb)[c] : static_cast<const float*>(zb)[c];
 
   // every row block of the sample in registers, all loads issued before any MFMA: each
   // block is read once (re-reading block J for every tile (I, J) left Large's forward at
   // 0.44 ms against 0.29)
   bf16x8 fr[FB][KS];
 #pragma unroll
-  for (int I = 0; I < FB; ++I) load_row_block<KS>(zb, F, I, rl, kg, fr[I]);
+  for (int I = 0; I < FB; ++I) load_row_block<KS, ZB>(zb, F, I, rl, kg, fr[I]);
 #pragma unroll
   for (int I = 0; I < FB; ++I) {
     if (32 * I >= F) break;
@@ -460,8 +474,9 @@ constexpr int kBwdChunk = 16;      // pair gradients per thread in flight at onc
 // Z rows 16 s + 8 kg .. + 7 of column n (clamped into dim) of one sample: no branch per load
 // (a branch around each load serializes them), the row clamped into the sample; rows past F
 // are zeroed when the fragments are packed.
-template <int KM, int KS>
-__device__ __forceinline__ void bwd_load_slab(const float* zb, int F, int n, int kg,
+// ZB: Z in bf16 (2-byte loads, widened exactly; the packing rounds them back unchanged).
+template <int KM, int KS, bool ZB>
+__device__ __forceinline__ void bwd_load_slab(const void* zb, int F, int n, int kg,
                                               float (&x)[KM][8]) {
   constexpr int dim = KS * 16;
   const int cn = n < dim ? n : dim - 1;
@@ -470,7 +485,8 @@ __device__ __forceinline__ void bwd_load_slab(const float* zb, int F, int n, int
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const int j = 16 * s + 8 * kg + e;
-      x[s][e] = zb[(j < F ? j : F - 1) * dim + cn];
+      const int at = (j < F ? j : F - 1) * dim + cn;
+      x[s][e] = ZB ? (float)static_cast<const __bf16*>(zb)[at] : static_cast<const float*>(zb)[at];
     }
   }
 }
@@ -524,10 +540,10 @@ __device__ __forceinline__ void bwd_write_pairs(__bf16* S, int P, int F, float r
 
 // At most 4 waves per SIMD as the occupancy target: aiming for more, the scheduler keeps
 // registers low by waiting for each Z load before the next (40 loads one at a time).
-template <int KM, int KS, int PS, bool OUTB>
+template <int KM, int KS, int PS, bool OUTB, bool ZB>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 4)))
 void interaction_bwd_mfma_kernel(
-    const float* __restrict__ Z, const float* __restrict__ dR, int64_t dr_stride,
+    const void* __restrict__ Z, const float* __restrict__ dR, int64_t dr_stride,
     int64_t batch, int F, int spb, void* __restrict__ dZ) {
   constexpr int dim = KS * 16;
   constexpr int NB = (dim + 31) / 32;      // 32-column slabs: waves per sample
@@ -563,7 +579,10 @@ void interaction_bwd_mfma_kernel(
   if (live) {
     const float* g = dR + b * dr_stride + dim;
     float v[kBwdChunk];
-    bwd_load_slab<KM, KS>(Z + b * (int64_t)F * dim, F, n, kg, x);
+    const int64_t zo = b * (int64_t)F * dim;
+    bwd_load_slab<KM, KS, ZB>(ZB ? static_cast<const void*>(static_cast<const __bf16*>(Z) + zo)
+                                 : static_cast<const void*>(static_cast<const float*>(Z) + zo),
+                              F, n, kg, x);
     bwd_load_pairs<PS, NT>(g, P, F, rcpF, 0, t, v);
     bwd_write_pairs<PS, NT, KM>(S, P, F, rcpF, 0, t, v);
     for (int q0 = kBwdChunk * NT; q0 < P; q0 += kBwdChunk * NT) {
@@ -736,10 +755,13 @@ bool interaction_f32_supported(int F, int dim, int pairs) {
 
 namespace {
 
+// z_bf16 (strict pairs, matrix-core compute only; the caller checks): Z held in bf16.
 template <int PS>
-hipError_t interaction_fwd(const float* Z, int64_t batch, int F, int dim, bool bf16, float* R,
-                           int64_t r_stride, hipStream_t s) {
+hipError_t interaction_fwd(const void* Zv, bool z_bf16, int64_t batch, int F, int dim, bool bf16,
+                           float* R, int64_t r_stride, hipStream_t s) {
+  if (z_bf16 && (!bf16 || PS != kStrict)) return hipErrorInvalidValue;
   if (batch == 0) return hipSuccess;
+  const float* Z = static_cast<const float*>(Zv);   // fp32 Z (the paths below that take it)
   if (!bf16) {
     if (lanes_shape(F, dim, PS)) {
       const int P = num_dots<PS>(F);        // the forward's LDS partials
@@ -759,21 +781,34 @@ hipError_t interaction_fwd(const float* Z, int64_t batch, int F, int dim, bool b
   }
   const int FB = (F + 31) / 32, KS = dim / 16;
   const int64_t blocks = (batch + 3) / 4;
-  CTR_FB_DISPATCH(FB, {
-    switch (KS) {
-      case 1: interaction_fwd_mfma_kernel<FB, 1, PS><<<(unsigned)blocks, kThreads, 0, s>>>(Z, batch, F, R, r_stride); break;
-      case 2: interaction_fwd_mfma_kernel<FB, 2, PS><<<(unsigned)blocks, kThreads, 0, s>>>(Z, batch, F, R, r_stride); break;
-      case 4: interaction_fwd_mfma_kernel<FB, 4, PS><<<(unsigned)blocks, kThreads, 0, s>>>(Z, batch, F, R, r_stride); break;
-      default: interaction_fwd_mfma_kernel<FB, 8, PS><<<(unsigned)blocks, kThreads, 0, s>>>(Z, batch, F, R, r_stride); break;
+#define CTR_FWD_MFMA(ZB_)                                                                   \
+  CTR_FB_DISPATCH(FB, {                                                                     \
+    switch (KS) {                                                                           \
+      case 1: interaction_fwd_mfma_kernel<FB, 1, PS, ZB_><<<(unsigned)blocks, kThreads, 0, s>>>(Zv, batch, F, R, r_stride); break; \
+      case 2: interaction_fwd_mfma_kernel<FB, 2, PS, ZB_><<<(unsigned)blocks, kThreads, 0, s>>>(Zv, batch, F, R, r_stride); break; \
+      case 4: interaction_fwd_mfma_kernel<FB, 4, PS, ZB_><<<(unsigned)blocks, kThreads, 0, s>>>(Zv, batch, F, R, r_stride); break; \
+      default: interaction_fwd_mfma_kernel<FB, 8, PS, ZB_><<<(unsigned)blocks, kThreads, 0, s>>>(Zv, batch, F, R, r_stride); break; \
+    }                                                                                       \
+  })
+  if constexpr (PS == kStrict) {
+    if (z_bf16) {
+      CTR_FWD_MFMA(true);
+      return hipGetLastError();
     }
-  });
+  }
+  CTR_FWD_MFMA(false);
+#undef CTR_FWD_MFMA
   return hipGetLastError();
 }
 
 template <int PS>
-hipError_t interaction_bwd(const float* Z, const float* dR, int64_t dr_stride, int64_t batch,
-                           int F, int dim, bool bf16, bool out_bf16, void* dZv, hipStream_t s) {
+hipError_t interaction_bwd(const void* Zv, bool z_bf16, const float* dR, int64_t dr_stride,
+                           int64_t batch, int F, int dim, bool bf16, bool out_bf16, void* dZv,
+                           hipStream_t s) {
+  // a bf16 Z is read by the matrix-core kernel of the strict pairs with a bf16 dZ only
+  if (z_bf16 && (!bf16 || PS != kStrict || !out_bf16)) return hipErrorInvalidValue;
   if (batch == 0) return hipSuccess;
+  const float* Z = static_cast<const float*>(Zv);   // fp32 Z (the paths below that take it)
   const int P = num_pairs<PS>(F);
   float* dZ = static_cast<float*>(dZv);
   if (!bf16) {
@@ -812,14 +847,19 @@ hipError_t interaction_bwd(const float* Z, const float* dR, int64_t dr_stride, i
   const int64_t blocks = (batch + spb - 1) / spb;
   const unsigned threads = (unsigned)(spb * NB * 64);
   const int KS = dim / 16;
-#define CTR_BWD_MFMA_KS(KM_, KS_)                                                              \
-  do {                                                                                         \
-    if (out_bf16)                                                                              \
-      interaction_bwd_mfma_kernel<KM_, KS_, PS, true><<<(unsigned)blocks, threads, lds, s>>>(  \
-          Z, dR, dr_stride, batch, F, spb, dZv);                                               \
-    else                                                                                       \
-      interaction_bwd_mfma_kernel<KM_, KS_, PS, false><<<(unsigned)blocks, threads, lds, s>>>( \
-          Z, dR, dr_stride, batch, F, spb, dZv);                                               \
+  // a bf16 Z: strict pairs only (the pooled step's), with a bf16 dZ
+  const bool zb = PS == kStrict && z_bf16;
+#define CTR_BWD_MFMA_KS(KM_, KS_)                                                                  \
+  do {                                                                                             \
+    if (zb && out_bf16)                                                                            \
+      interaction_bwd_mfma_kernel<KM_, KS_, PS, true, PS == kStrict><<<(unsigned)blocks, threads, lds, s>>>( \
+          Zv, dR, dr_stride, batch, F, spb, dZv);                                                  \
+    else if (out_bf16)                                                                             \
+      interaction_bwd_mfma_kernel<KM_, KS_, PS, true, false><<<(unsigned)blocks, threads, lds, s>>>( \
+          Zv, dR, dr_stride, batch, F, spb, dZv);                                                  \
+    else                                                                                           \
+      interaction_bwd_mfma_kernel<KM_, KS_, PS, false, false><<<(unsigned)blocks, threads, lds, s>>>( \
+          Zv, dR, dr_stride, batch, F, spb, dZv);                                                  \
   } while (0)
 #define CTR_BWD_MFMA(KM_)                            \
   do {                                               \
@@ -847,21 +887,25 @@ hipError_t interaction_bwd(const float* Z, const float* dR, int64_t dr_stride, i
 
 }  // namespace
 
-hipError_t launch_interaction_fwd(const float* Z, int64_t batch, int F, int dim, bool bf16,
-                                  int pairs, float* R, int64_t r_stride, hipStream_t s) {
-  if (pairs == kGram) return interaction_fwd<kGram>(Z, batch, F, dim, bf16, R, r_stride, s);
-  if (pairs == kSelf) return interaction_fwd<kSelf>(Z, batch, F, dim, bf16, R, r_stride, s);
-  return interaction_fwd<kStrict>(Z, batch, F, dim, bf16, R, r_stride, s);
+hipError_t launch_interaction_fwd(const void* Z, bool z_bf16, int64_t batch, int F, int dim,
+                                  bool bf16, int pairs, float* R, int64_t r_stride,
+                                  hipStream_t s) {
+  if (pairs == kGram)
+    return interaction_fwd<kGram>(Z, false, batch, F, dim, bf16, R, r_stride, s);
+  if (pairs == kSelf)
+    return interaction_fwd<kSelf>(Z, false, batch, F, dim, bf16, R, r_stride, s);
+  return interaction_fwd<kStrict>(Z, z_bf16, batch, F, dim, bf16, R, r_stride, s);
 }
 
-hipError_t launch_interaction_bwd(const float* Z, const float* dR, int64_t dr_stride,
-                                  int64_t batch, int F, int dim, bool bf16, int pairs,
-                                  bool out_bf16, void* dZ, hipStream_t s) {
+hipError_t launch_interaction_bwd(const void* Z, bool z_bf16, const float* dR,
+                                  int64_t dr_stride, int64_t batch, int F, int dim, bool bf16,
+                                  int pairs, bool out_bf16, void* dZ, hipStream_t s) {
   if (pairs == kGram)
-    return interaction_bwd<kGram>(Z, dR, dr_stride, batch, F, dim, bf16, out_bf16, dZ, s);
+    return interaction_bwd<kGram>(Z, false, dR, dr_stride, batch, F, dim, bf16, out_bf16, dZ, s);
   if (pairs == kSelf)
-    return interaction_bwd<kSelf>(Z, dR, dr_stride, batch, F, dim, bf16, out_bf16, dZ, s);
-  return interaction_bwd<kStrict>(Z, dR, dr_stride, batch, F, dim, bf16, out_bf16, dZ, s);
+    return interaction_bwd<kSelf>(Z, false, dR, dr_stride, batch, F, dim, bf16, out_bf16, dZ, s);
+  return interaction_bwd<kStrict>(Z, z_bf16, dR, dr_stride, batch, F, dim, bf16, out_bf16, dZ,
+                                  s);
 }
 
 hipError_t launch_fm_fwd(const float* Z, int64_t batch, int F, int dim, float* out,

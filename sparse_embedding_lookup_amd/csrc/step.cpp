@@ -66,9 +66,11 @@ int32_t forward_part(const ctr_step_t* d, int set, hipStream_t s, void* mark_beg
     const int64_t F = (int64_t)d->num_tables + 1;
     CTR_TRY(mark(mark_begin, s));
     size_t wsb = d->ws_pool_bytes;
+    const size_t zsz = d->z_dtype == CTR_BF16 ? 2 : 4;      // Z[:, 1 + t, :]: past the dense row
     CTR_TRY(ctr_embbag_fwd(d->table, d->dtype, d->total_rows, d->dim, d->row_base, d->num_tables,
                            d->indices, d->index_type, d->nnz, d->offsets, d->batch,
-                           d->Z + d->dim, F * d->dim, d->dim, d->ws_pool, &wsb, s));
+                           static_cast<char*>(d->Z) + (size_t)d->dim * zsz, d->z_dtype,
+                           F * d->dim, d->dim, d->ws_pool, &wsb, s));
     return mark(mark_end, s);
   }
   CTR_TRY(ctr_gather_rows(d->table, d->dtype, d->total_rows, d->dim, d->uniq[set],
@@ -76,7 +78,8 @@ int32_t forward_part(const ctr_step_t* d, int set, hipStream_t s, void* mark_beg
   CTR_TRY(mark(mark_begin, s));
   size_t wsb = d->ws_pool_bytes;
   CTR_TRY(ctr_embbag_fwd(d->E, CTR_F32, d->nnz, d->dim, nullptr, 1, d->inverse[set], CTR_I32,
-                         d->nnz, d->offsets, d->nnz, d->out, d->dim, 0, d->ws_pool, &wsb, s));
+                         d->nnz, d->offsets, d->nnz, d->out, CTR_F32, d->dim, 0, d->ws_pool,
+                         &wsb, s));
   return mark(mark_end, s);
 }
 
@@ -84,10 +87,10 @@ int32_t forward_part(const ctr_step_t* d, int set, hipStream_t s, void* mark_beg
 int32_t interaction_part(const ctr_step_t* d, hipStream_t s) {
   if (d->kind != CTR_STEP_POOLED_INTERACTION) return CTR_OK;
   const int64_t F = (int64_t)d->num_tables + 1;
-  CTR_TRY(ctr_dot_interaction_fwd(d->Z, d->batch, (int32_t)F, d->dim, d->compute, d->R,
-                                  d->dim + F * (F - 1) / 2, s));
-  return ctr_dot_interaction_bwd(d->Z, d->dR, d->dim + F * (F - 1) / 2, d->batch, (int32_t)F,
-                                 d->dim, d->compute, d->grad_dtype, d->dZ, s);
+  CTR_TRY(ctr_dot_interaction_fwd(d->Z, d->z_dtype, d->batch, (int32_t)F, d->dim, d->compute,
+                                  d->R, d->dim + F * (F - 1) / 2, s));
+  return ctr_dot_interaction_bwd(d->Z, d->z_dtype, d->dR, d->dim + F * (F - 1) / 2, d->batch,
+                                 (int32_t)F, d->dim, d->compute, d->grad_dtype, d->dZ, s);
 }
 
 // The backward with the SGD update of the touched rows; with mark_stage CTR_MARK_BACKWARD the

@@ -63,7 +63,7 @@ class CtrStep(ctypes.Structure):
                 ("ws_unique2", _P), ("ws_unique2_bytes", ctypes.c_size_t),
                 ("mark_stage", ctypes.c_int32), ("max_table_rows", ctypes.c_int64),
                 ("ws_pool", _P), ("ws_pool_bytes", ctypes.c_size_t),
-                ("src_layout", ctypes.c_int32)]
+                ("src_layout", ctypes.c_int32), ("z_dtype", ctypes.c_int32)]
 
 _lib = None
 
@@ -97,8 +97,8 @@ def load() -> ctypes.CDLL:
         "ctr_unique_ids": (i32, [P, i32, i64, P, i64, i32, P, i64, i64, i64, P, P, P, P, P, P,
                                  i32, P, PS, P]),
         "ctr_gather_rows": (i32, [P, i32, i64, i32, P, P, i64, P, P]),
-        "ctr_embbag_fwd": (i32, [P, i32, i64, i32, P, i32, P, i32, i64, P, i64, P, i64, i64, P,
-                                 PS, P]),
+        "ctr_embbag_fwd": (i32, [P, i32, i64, i32, P, i32, P, i32, i64, P, i64, P, i32, i64, i64,
+                                 P, PS, P]),
         "ctr_embbag_bwd": (i32, [P, i64, i64, P, i64, i32, i32, i64, P, P, P, P, P, P, PS, P]),
         "ctr_embbag_bwd_sgd": (i32, [P, i32, i64, i64, P, i64, i32, i64, P, i32, P, P, i32, i64,
                                      i32, P, f32, i32, u64, P, P, PS, P]),
@@ -118,10 +118,10 @@ def load() -> ctypes.CDLL:
         "ctr_dict_lookup": (i32, [P, i64, P, i64, P, P]),
         "ctr_dict_embbag_fwd": (i32, [P, i64, P, i64, i32, P, i64, P, i64, i32, i32, P, i64,
                                       i64, P]),
-        "ctr_dot_interaction_fwd": (i32, [P, i64, i32, i32, i32, P, i64, P]),
+        "ctr_dot_interaction_fwd": (i32, [P, i32, i64, i32, i32, i32, P, i64, P]),
         "ctr_embbag_interaction_fwd": (i32, [P, i32, i64, i32, P, i32, P, i32, i64, P, i64, P,
                                              i32, P, i64, P]),
-        "ctr_dot_interaction_bwd": (i32, [P, P, i64, i64, i32, i32, i32, i32, P, P]),
+        "ctr_dot_interaction_bwd": (i32, [P, i32, P, i64, i64, i32, i32, i32, i32, P, P]),
         "ctr_init_tables_hash": (i32, [P, i32, i32, P, i32, u64, P]),
         "ctr_validate_csr": (i32, [P, i32, i64, P, i64, i32, P, i64, P, P]),
         "ctr_step_run": (i32, [P, i64, i32, P, P, P, P, P, P]),
@@ -138,6 +138,12 @@ def load() -> ctypes.CDLL:
         fn.argtypes = args
     _lib = lib
     return lib
+
+
+def _require_f32(Z: torch.Tensor, fn: str) -> None:
+    """The entry points whose Z is fp32 only (their C signature carries no Z type)."""
+    if Z.dtype != torch.float32:
+        raise TypeError("%s takes an fp32 Z, not %s" % (fn, Z.dtype))
 
 
 def _ptr(t: Optional[torch.Tensor]):
@@ -288,7 +294,7 @@ def embbag_fwd_workspace_bytes(nnz: int, dim: int) -> int:
     """Workspace of ctr_embbag_fwd (the library's two-call query)."""
     wsb = ctypes.c_size_t(0)
     _check("ctr_embbag_fwd", load().ctr_embbag_fwd(None, CTR_F32, 0, dim, None, 1, None, CTR_I64,
-                                                   nnz, None, 0, None, 0, 0, None,
+                                                   nnz, None, 0, None, CTR_F32, 0, 0, None,
                                                    ctypes.byref(wsb), None))
     return wsb.value
 
@@ -298,8 +304,9 @@ def ctr_embbag_fwd(table: torch.Tensor, indices: torch.Tensor, offsets: torch.Te
                    out_stride_t: int, row_base: Optional[torch.Tensor] = None,
                    workspace: Optional[torch.Tensor] = None, stream=None,
                    prepare: bool = False):
-    """Sum pooling of the bags into out; ``workspace`` (uint8, from embbag_fwd_workspace_bytes)
-    holds the partial sums of bags longer than 4096 occurrences (allocated when None)."""
+    """Sum pooling of the bags into out (fp32, or bf16: the fp32 sums rounded once at the
+    store); ``workspace`` (uint8, from embbag_fwd_workspace_bytes) holds the partial sums of
+    bags longer than 4096 occurrences (allocated when None)."""
     total_rows, dim = table.shape
     nnz = indices.numel()
     if workspace is None:
@@ -307,7 +314,7 @@ def ctr_embbag_fwd(table: torch.Tensor, indices: torch.Tensor, offsets: torch.Te
     wsb = ctypes.c_size_t(workspace.numel())
     args = (_ptr(table), _dtype_code(table), total_rows, dim, _ptr(row_base), num_tables,
             _ptr(indices), _index_code(indices), nnz, _ptr(offsets), batch, _ptr(out),
-            out_stride_b, out_stride_t, _ptr(workspace), ctypes.byref(wsb))
+            _dtype_code(out), out_stride_b, out_stride_t, _ptr(workspace), ctypes.byref(wsb))
     return _run("ctr_embbag_fwd", args, stream, prepare, out)
 
 
@@ -419,7 +426,7 @@ def ctr_dot_interaction_fwd(Z: torch.Tensor, compute: int = CTR_F32,
     P = F * (F - 1) // 2
     if R is None:
         R = torch.empty((B, d + P), dtype=torch.float32, device=Z.device)
-    args = (_ptr(Z), B, F, d, compute, _ptr(R), R.stride(0))
+    args = (_ptr(Z), _dtype_code(Z), B, F, d, compute, _ptr(R), R.stride(0))
     return _run("ctr_dot_interaction_fwd", args, stream, prepare, R)
 
 
@@ -432,6 +439,7 @@ def ctr_embbag_interaction_fwd(table: torch.Tensor, indices: torch.Tensor,
     (the dense vectors) is an input."""
     total_rows, dim = table.shape
     B, F, d = Z.shape
+    _require_f32(Z, "ctr_embbag_interaction_fwd")
     assert d == dim and Z.is_contiguous()
     P = F * (F - 1) // 2
     if R is None:
@@ -445,11 +453,13 @@ def ctr_embbag_interaction_fwd(table: torch.Tensor, indices: torch.Tensor,
 def ctr_dot_interaction_bwd(Z: torch.Tensor, dR: torch.Tensor, compute: int = CTR_F32,
                             dZ: Optional[torch.Tensor] = None, stream=None,
                             prepare: bool = False):
-    """dZ fp32, or bf16 when ``dZ`` is a bf16 tensor (compute must be CTR_BF16)."""
+    """dZ fp32, or bf16 when ``dZ`` is a bf16 tensor (compute must be CTR_BF16).  Z may be
+    bf16 (compute CTR_BF16, dZ bf16)."""
     B, F, d = Z.shape
     if dZ is None:
         dZ = torch.empty_like(Z)
-    args = (_ptr(Z), _ptr(dR), dR.stride(0), B, F, d, compute, _dtype_code(dZ), _ptr(dZ))
+    args = (_ptr(Z), _dtype_code(Z), _ptr(dR), dR.stride(0), B, F, d, compute, _dtype_code(dZ),
+            _ptr(dZ))
     return _run("ctr_dot_interaction_bwd", args, stream, prepare, dZ)
 
 
@@ -458,6 +468,7 @@ def ctr_dot_interaction_self_fwd(Z: torch.Tensor, compute: int = CTR_F32,
                                  prepare: bool = False):
     """Pair dots with self-dots (i >= j), P = F(F+1)/2: R = [dense | pairs]."""
     B, F, d = Z.shape
+    _require_f32(Z, "ctr_dot_interaction_self_fwd")
     P = F * (F + 1) // 2
     if R is None:
         R = torch.empty((B, d + P), dtype=torch.float32, device=Z.device)
@@ -470,6 +481,7 @@ def ctr_dot_interaction_self_bwd(Z: torch.Tensor, dR: torch.Tensor, compute: int
                                  prepare: bool = False):
     """dZ fp32, or bf16 when ``dZ`` is a bf16 tensor (compute must be CTR_BF16)."""
     B, F, d = Z.shape
+    _require_f32(Z, "ctr_dot_interaction_self_bwd")
     if dZ is None:
         dZ = torch.empty_like(Z)
     args = (_ptr(Z), _ptr(dR), dR.stride(0), B, F, d, compute, _dtype_code(dZ), _ptr(dZ))
@@ -481,6 +493,7 @@ def ctr_dot_interaction_gram_fwd(Z: torch.Tensor, compute: int = CTR_F32,
                                  prepare: bool = False):
     """The whole Gram matrix, P = F^2 row-major after the dense slot: R = [dense | Z Z^T]."""
     B, F, d = Z.shape
+    _require_f32(Z, "ctr_dot_interaction_gram_fwd")
     if R is None:
         R = torch.empty((B, d + F * F), dtype=torch.float32, device=Z.device)
     args = (_ptr(Z), B, F, d, compute, _ptr(R), R.stride(0))
@@ -493,6 +506,7 @@ def ctr_dot_interaction_gram_bwd(Z: torch.Tensor, dR: torch.Tensor, compute: int
     """dZ_i = sum_j (dG_ij + dG_ji) z_j (+ dense on slot 0); fp32, or bf16 when ``dZ`` is a
     bf16 tensor (compute must be CTR_BF16)."""
     B, F, d = Z.shape
+    _require_f32(Z, "ctr_dot_interaction_gram_bwd")
     if dZ is None:
         dZ = torch.empty_like(Z)
     args = (_ptr(Z), _ptr(dR), dR.stride(0), B, F, d, compute, _dtype_code(dZ), _ptr(dZ))
@@ -503,6 +517,7 @@ def ctr_fm_interaction_fwd(Z: torch.Tensor, out: Optional[torch.Tensor] = None, 
                            prepare: bool = False):
     """Sum of all pair dots per sample by the squared-norm identity: out [B]."""
     B, F, d = Z.shape
+    _require_f32(Z, "ctr_fm_interaction_fwd")
     if out is None:
         out = torch.empty((B,), dtype=torch.float32, device=Z.device)
     args = (_ptr(Z), B, F, d, _ptr(out))
@@ -513,6 +528,7 @@ def ctr_fm_interaction_bwd(Z: torch.Tensor, dout: torch.Tensor,
                            dZ: Optional[torch.Tensor] = None, stream=None,
                            prepare: bool = False):
     B, F, d = Z.shape
+    _require_f32(Z, "ctr_fm_interaction_bwd")
     if dZ is None:
         dZ = torch.empty_like(Z)
     args = (_ptr(Z), _ptr(dout), B, F, d, _ptr(dZ))

@@ -38,7 +38,7 @@ class FrontEnd:
                  fused: bool = True, keep_grads: bool = False, pipelined: bool = False,
                  rounding: str = "nearest", sr_seed: int = SR_SEED, pad_r: bool = False,
                  fused_fwd: bool = False, lean_unique: bool = False,
-                 src_rows: Optional[bool] = None):
+                 src_rows: Optional[bool] = None, z_bf16: bool = False):
         """fused: the backward applies the sparse SGD as each row gradient completes
         (ctr_embbag_bwd_sgd); otherwise ctr_embbag_bwd then ctr_sparse_sgd.  keep_grads: also
         keep the per-row gradients in self.row_grads (always kept when not fused).
@@ -58,7 +58,10 @@ class FrontEnd:
         permutation or segment offsets, and no occurrence payload through the sort.
         src_rows: sorted_src holds 8-byte row entries (CTR_SRC_ROWS) instead of 16-byte
         (u, bag, key) quadruples; only for the fused update without kept gradients, which is
-        also the default (None) then."""
+        also the default (None) then.
+        z_bf16: Z (the dense and pooled vectors) is held in bf16 (matrix-core workloads with the
+        two-call forward): the pooling rounds its fp32 sums once at the store, the interaction
+        reads the same operands it would round from fp32, in half the bytes."""
         assert rounding in ("nearest", "stochastic")
         assert rounding == "nearest" or w.dtype in ("bf16", "f16"), \
             "stochastic rounding: bf16 or fp16 tables"
@@ -71,6 +74,9 @@ class FrontEnd:
         self.pipelined = pipelined
         self.fused = fused
         self.fused_fwd = bool(fused_fwd and w.interaction)
+        assert not z_bf16 or (w.interaction and w.compute == "bf16" and not self.fused_fwd), \
+            "a bf16 Z: matrix-core interaction and the two-call forward"
+        self.z_bf16 = z_bf16
         self.keep_grads = keep_grads or not fused
         if src_rows is None:
             src_rows = self.fused and not self.keep_grads
@@ -91,7 +97,8 @@ class FrontEnd:
         B, T, d = w.batch, w.num_tables, w.dim
         if w.interaction:
             F = w.F
-            self.Z = torch.empty((B, F, d), dtype=torch.float32, device=self.device)
+            self.Z = torch.empty((B, F, d), dtype=torch.bfloat16 if z_bf16 else torch.float32,
+                                 device=self.device)
             self.Z[:, 0, :].copy_(_dev(w.dense, self.device))        # batch upload
             width = d + w.P
             stride = (width + 3) // 4 * 4 if pad_r else width
@@ -169,7 +176,8 @@ class FrontEnd:
                 self.table, self.indices, self.offsets, w.batch, w.num_tables, self.Z[:, 1:, :],
                 F * d, d, row_base=self.row_base, workspace=self.ws_pool, **P)
             self._c_interaction_fwd = ctr.ctr_dot_interaction_fwd(self.Z, self.compute, self.R, **P)
-            self._c_embbag_interaction_fwd = ctr.ctr_embbag_interaction_fwd(
+            # the fused forward writes an fp32 Z
+            self._c_embbag_interaction_fwd = None if self.z_bf16 else ctr.ctr_embbag_interaction_fwd(
                 self.table, self.indices, self.offsets, self.Z, self.compute, self.R,
                 row_base=self.row_base, **P)
             self._c_interaction_bwd = ctr.ctr_dot_interaction_bwd(self.Z, self.dR, self.compute,
@@ -447,6 +455,7 @@ class FrontEnd:
         if w.interaction:
             d.Z, d.R, d.dR, d.dZ = P(self.Z), P(self.R), P(self.dR), P(self.dZ)
             d.grad_dtype = ctr._dtype_code(self.dZ)
+            d.z_dtype = ctr._dtype_code(self.Z)
         else:
             d.E, d.out, d.dout = P(self.E), P(self.out), P(self.dout)
         d.row_grads = P(self.row_grads)

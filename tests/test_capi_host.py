@@ -89,21 +89,21 @@ def test_unique_workspace_query_and_bad_args():
 def test_embbag_fwd_bad_args():
     lib = _lib()
     ok = dict(table=FAKE, dtype=0, rows=100, dim=16, rb=None, T=1, idx=FAKE, it=1, nnz=10,
-              off=FAKE, B=10, out=FAKE, sb=16, st=0, ws=FAKE, wsb=1 << 20)
+              off=FAKE, B=10, out=FAKE, ot=0, sb=16, st=0, ws=FAKE, wsb=1 << 20)
 
     def call(**kw):
         a = dict(ok, **kw)
         wsb = ctypes.c_size_t(a["wsb"])
         return lib.ctr_embbag_fwd(a["table"], a["dtype"], a["rows"], a["dim"], a["rb"], a["T"],
                                   a["idx"], a["it"], a["nnz"], a["off"], a["B"], a["out"],
-                                  a["sb"], a["st"], a["ws"], ctypes.byref(wsb), None)
+                                  a["ot"], a["sb"], a["st"], a["ws"], ctypes.byref(wsb), None)
 
     # the workspace query needs nnz and dim only: 256 bytes up to 4096 occurrences, then the
     # long bags' chunk partials
     q = ctypes.c_size_t(0)
-    assert lib.ctr_embbag_fwd(None, 0, 0, 16, None, 1, None, 1, 4096, None, 0, None, 0, 0, None,
-                              ctypes.byref(q), None) == ctr.CTR_OK and q.value == 256
-    assert lib.ctr_embbag_fwd(None, 0, 0, 16, None, 1, None, 1, 1 << 20, None, 0, None, 0, 0,
+    assert lib.ctr_embbag_fwd(None, 0, 0, 16, None, 1, None, 1, 4096, None, 0, None, 0, 0, 0,
+                              None, ctypes.byref(q), None) == ctr.CTR_OK and q.value == 256
+    assert lib.ctr_embbag_fwd(None, 0, 0, 16, None, 1, None, 1, 1 << 20, None, 0, None, 0, 0, 0,
                               None, ctypes.byref(q), None) == ctr.CTR_OK
     assert q.value == 256 + 256 * 8 + 256 * 2 * 16 * 4
     assert ctr.embbag_fwd_workspace_bytes(1 << 20, 16) == q.value
@@ -119,6 +119,10 @@ def test_embbag_fwd_bad_args():
     assert call(table=MISALIGNED) == ctr.CTR_ERR_UNSUPPORTED
     assert call(out=MISALIGNED) == ctr.CTR_ERR_UNSUPPORTED
     assert call(sb=18) == ctr.CTR_ERR_UNSUPPORTED
+    # bf16 pooled vectors: stores of up to 8 values, so strides in multiples of 8
+    assert call(ot=ctr.CTR_BF16, sb=20) == ctr.CTR_ERR_UNSUPPORTED
+    assert call(ot=7) == ctr.CTR_ERR_INVALID_ARGUMENT
+    assert b"out_dtype" in lib.ctr_last_error_message()
     assert call(it=3) == ctr.CTR_ERR_INVALID_ARGUMENT
     assert call(nnz=-1) == ctr.CTR_ERR_INVALID_ARGUMENT
     assert call(off=None) == ctr.CTR_ERR_INVALID_ARGUMENT
@@ -188,14 +192,18 @@ def test_embbag_bwd_workspace_and_bad_args():
 
 def test_interaction_bad_args():
     lib = _lib()
-    f = lib.ctr_dot_interaction_fwd
+    f = lambda Z, *a, zt=0: lib.ctr_dot_interaction_fwd(Z, zt, *a)
     assert f(FAKE, 10, 1, 16, 0, FAKE, 100, None) == ctr.CTR_ERR_INVALID_ARGUMENT    # F < 2
     assert f(FAKE, 10, 5, 16, 0, FAKE, 20, None) == ctr.CTR_ERR_INVALID_ARGUMENT     # stride
     assert f(FAKE, 10, 5, 16, 9, FAKE, 26, None) == ctr.CTR_ERR_INVALID_ARGUMENT     # compute
     assert f(FAKE, 10, 5, 24, 1, FAKE, 40, None) == ctr.CTR_ERR_UNSUPPORTED          # bf16 dim
     assert f(FAKE, 10, 200, 128, 1, FAKE, 30000, None) == ctr.CTR_ERR_UNSUPPORTED    # bf16 F
     assert f(MISALIGNED, 10, 5, 16, 1, FAKE, 26, None) == ctr.CTR_ERR_UNSUPPORTED
-    b = lib.ctr_dot_interaction_bwd
+    # a bf16 Z: only for the matrix-core interaction; an unknown Z type
+    assert f(FAKE, 10, 5, 16, 0, FAKE, 26, None, zt=ctr.CTR_BF16) == ctr.CTR_ERR_UNSUPPORTED
+    assert f(FAKE, 10, 5, 16, 1, FAKE, 26, None, zt=5) == ctr.CTR_ERR_INVALID_ARGUMENT
+    assert b"z_dtype" in lib.ctr_last_error_message()
+    b = lambda Z, *a, zt=0: lib.ctr_dot_interaction_bwd(Z, zt, *a)
     assert b(FAKE, None, 26, 10, 5, 16, 0, 0, FAKE, None) == ctr.CTR_ERR_INVALID_ARGUMENT  # dR NULL
     # dZ type: an unknown code, and bf16 storage without bf16 compute
     assert b(FAKE, FAKE, 26, 10, 5, 16, 1, 7, FAKE, None) == ctr.CTR_ERR_INVALID_ARGUMENT
@@ -205,6 +213,11 @@ def test_interaction_bad_args():
     assert b(FAKE, FAKE, 26, 10, 5, 16, 1, 1, MISALIGNED, None) == ctr.CTR_ERR_UNSUPPORTED
     assert b"dZ is not 16-byte aligned" in lib.ctr_last_error_message()
     assert b(FAKE, FAKE, 26, 10, 5, 16, 1, 0, MISALIGNED, None) == ctr.CTR_ERR_UNSUPPORTED
+    # a bf16 Z takes a bf16 dZ, and bf16 compute
+    assert b(FAKE, FAKE, 26, 10, 5, 16, 1, 0, FAKE, None, zt=ctr.CTR_BF16) == \
+        ctr.CTR_ERR_UNSUPPORTED
+    assert b(FAKE, FAKE, 26, 10, 5, 16, 0, 0, FAKE, None, zt=ctr.CTR_BF16) == \
+        ctr.CTR_ERR_UNSUPPORTED
 
 
 def test_sgd_gather_init_validate_bad_args():

@@ -361,6 +361,27 @@ def test_embbag_fwd_matches_oracle(name, itype):
     np.testing.assert_array_equal(got[single], want[single])
 
 
+@pytest.mark.parametrize("name", FWD_CASES)
+def test_embbag_fwd_bf16_out_is_the_rounded_fp32_out(name):
+    """Pooled vectors stored in bf16 are the fp32 pooling's vectors rounded to nearest-even,
+    bit for bit (the sums stay fp32 until the one rounding at the store), empty bags and long
+    bags included; the layout of Z[:, 1:, :] with its strides in elements."""
+    rows, dim, dtype, ids, off, B, T = _fwd_case(name)
+    if dim % 8:
+        pytest.skip("bf16 pooled vectors take rows of a multiple of 8 values")
+    say("embbag_fwd bf16 out", name, len(ids))
+    t = gpu_table(rows, dim, dtype, 11)
+    tab = orc.Table(rows, dim, dtype, 11)
+    rb, gi = dev(tab.row_base), dev(ids.astype(np.int64))
+    z32 = torch.full((B, T + 1, dim), float("nan"), dtype=torch.float32, device=DEV)
+    z16 = torch.full((B, T + 1, dim), float("nan"), dtype=torch.bfloat16, device=DEV)
+    ctr.ctr_embbag_fwd(t, gi, dev(off), B, T, z32[:, 1:, :], (T + 1) * dim, dim, row_base=rb)
+    ctr.ctr_embbag_fwd(t, gi, dev(off), B, T, z16[:, 1:, :], (T + 1) * dim, dim, row_base=rb)
+    torch.cuda.synchronize()
+    assert torch.isnan(z16[:, 0, :].float()).all()          # the dense row is not touched
+    assert torch.equal(z16[:, 1:, :], z32[:, 1:, :].to(torch.bfloat16))
+
+
 # ----------------------------------------------------------------------------- interaction
 INTER_CASES = [
     ("f32", 128, 5, 16), ("f32", 2048, 9, 64), ("f32", 77, 2, 4), ("f32", 33, 27, 128),
@@ -374,6 +395,26 @@ INTER_CASES = [
     ("bf16", 21, 16, 32), ("bf16", 23, 17, 64), ("bf16", 30, 33, 128), ("bf16", 17, 112, 64),
     ("bf16", 7, 128, 128), ("bf16", 11, 128, 16),
 ]
+
+
+@pytest.mark.parametrize("B,F,d", [(b, f, dd) for c, b, f, dd in INTER_CASES if c == "bf16"])
+def test_interaction_bf16_z_matches_rounded_fp32_z(B, F, d):
+    """The matrix-core interaction reading Z held in bf16 gives, bit for bit, what it gives
+    reading the same values in fp32 (it rounds fp32 operands to the same bf16): R with the
+    widened dense passthrough, and the bf16 dZ."""
+    say("interaction bf16 Z", B, F, d)
+    rng = np.random.default_rng(5)
+    zb = dev(rng.standard_normal((B, F, d)).astype(np.float32)).to(torch.bfloat16)
+    dR = dev(rng.standard_normal((B, d + F * (F - 1) // 2)).astype(np.float32))
+    R16 = ctr.ctr_dot_interaction_fwd(zb, ctr.CTR_BF16)
+    R32 = ctr.ctr_dot_interaction_fwd(zb.float(), ctr.CTR_BF16)
+    g16 = ctr.ctr_dot_interaction_bwd(zb, dR, ctr.CTR_BF16,
+                                      dZ=torch.empty(zb.shape, dtype=torch.bfloat16, device=DEV))
+    g32 = ctr.ctr_dot_interaction_bwd(zb.float(), dR, ctr.CTR_BF16,
+                                      dZ=torch.empty(zb.shape, dtype=torch.bfloat16, device=DEV))
+    torch.cuda.synchronize()
+    assert torch.equal(R16, R32)
+    assert torch.equal(g16, g32)
 
 
 def _inter_inputs(B, F, d, seed):
@@ -865,6 +906,48 @@ def test_row_entry_graph_matches_eager(name, schedule):
             np.testing.assert_array_equal(host(fa.dZ), host(fb.dZ))
         else:
             np.testing.assert_array_equal(host(fa.out), host(fb.out))
+
+
+@pytest.mark.parametrize("schedule", ["python", "serial", "overlap", "overlap2", "graph"])
+@pytest.mark.parametrize("name", ["criteo_b128", "large_t8_b512"])
+def test_bf16_z_steps_match_fp32_z_steps(name, schedule):
+    """Steps holding Z in bf16 (the pooling rounds its sums once at the store) leave the table,
+    dZ and the pair dots of R bit-identical to steps holding Z in fp32 (the matrix cores take
+    the same bf16 operands either way); R's dense passthrough is the dense vector in bf16."""
+    w = {"criteo_b128": lambda: workloads.criteo(batch=128),
+         "large_t8_b512": lambda: workloads.large(batch=512, tables=8, rows=400_000)}[name]()
+    say("bf16 Z steps", name, schedule)
+    pipelined = schedule not in ("python", "serial")
+    sched = "overlap" if schedule == "graph" else schedule
+    fa = FrontEnd(w, DEV, lean_unique=True, pipelined=pipelined)
+    fb = FrontEnd(w, DEV, lean_unique=True, pipelined=pipelined, z_bf16=True)
+    assert fb.Z.dtype == torch.bfloat16 and fa.Z.dtype == torch.float32
+    K = 4
+    g = fb.capture_native(K, sched) if schedule == "graph" else None
+    if pipelined:
+        fa.native_start(deep=schedule == "overlap2")
+        fb.native_start(deep=schedule == "overlap2")
+    d = w.dim
+    for k in range(2 if schedule == "graph" else 3):
+        for _ in range(K if schedule == "graph" else 1):
+            if schedule == "python":
+                fa.step()
+            else:
+                fa.step_native(sched)
+        if schedule == "python":
+            fb.step()
+        elif schedule == "graph":
+            if k:
+                fb.native_start()
+            g.replay()
+        else:
+            fb.step_native(sched)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(host(fa.R)[:, d:], host(fb.R)[:, d:])
+        np.testing.assert_array_equal(host(fb.R)[:, :d],
+                                      host(fa.Z[:, 0, :].to(torch.bfloat16).float()))
+        np.testing.assert_array_equal(host(fa.dZ.float()), host(fb.dZ.float()))
+        assert torch.equal(fa.table, fb.table), k
 
 
 @pytest.mark.parametrize("name", ["small_b256", "criteo_b128", "tensornet_b512"])
