@@ -540,7 +540,15 @@ __device__ __forceinline__ void bwd_write_pairs(__bf16* S, int P, int F, float r
 
 // At most 4 waves per SIMD as the occupancy target: aiming for more, the scheduler keeps
 // registers low by waiting for each Z load before the next (40 loads one at a time).
-template <int KM, int KS, int PS, bool OUTB, bool ZB>
+// Z held in bf16, staged (ZM = 2): a wave reads its slab's 16 KM rows x 32 columns with one
+// 16-byte load per 8 columns of a row (KM loads per lane, not 8 KM two-byte ones) into a
+// wave-private LDS image with rows kStagePitch values apart (an odd multiple of 4 bytes
+// over 8 rows, so the transposed reads of rows 8 apart fall in different banks), and takes
+// its fragments' 8-row columns from there.
+constexpr int kStagePitch = 36;
+
+// ZM: Z in fp32 (0), in bf16 read directly (1), or in bf16 staged through LDS (2).
+template <int KM, int KS, int PS, bool OUTB, int ZM>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 4)))
 void interaction_bwd_mfma_kernel(
     const void* __restrict__ Z, const float* __restrict__ dR, int64_t dr_stride,
@@ -559,6 +567,7 @@ void interaction_bwd_mfma_kernel(
   const int rl = lane & 31, kg = lane >> 5;
   const int n = 32 * nb + rl;              // column of Z (A row) of this lane
   __bf16* S = reinterpret_cast<__bf16*>(s_raw) + (size_t)sl * F * pitch;
+  constexpr bool ZB = ZM != 0;
   const int P = num_pairs<PS>(F);
   const float rcpF = 1.0f / (float)F;
   const int64_t b = (int64_t)blockIdx.x * spb + sl;
@@ -580,11 +589,43 @@ void interaction_bwd_mfma_kernel(
     const float* g = dR + b * dr_stride + dim;
     float v[kBwdChunk];
     const int64_t zo = b * (int64_t)F * dim;
-    bwd_load_slab<KM, KS, ZB>(ZB ? static_cast<const void*>(static_cast<const __bf16*>(Z) + zo)
-                                 : static_cast<const void*>(static_cast<const float*>(Z) + zo),
-                              F, n, kg, x);
-    bwd_load_pairs<PS, NT>(g, P, F, rcpF, 0, t, v);
-    bwd_write_pairs<PS, NT, KM>(S, P, F, rcpF, 0, t, v);
+    if constexpr (ZM == 2) {
+      // row r = task / 4 (clamped into the sample; rows past F are zeroed at the packing),
+      // columns 32 nb + 8 (task % 4) .. + 7 (clamped into the row, as the direct loads clamp
+      // their column)
+      const __bf16* zb = static_cast<const __bf16*>(Z) + zo;
+      const size_t soff = ((size_t)spb * F * pitch * 2 + 15) & ~(size_t)15;
+      __bf16* zst = reinterpret_cast<__bf16*>(s_raw + soff) + (size_t)wv * (16 * KM * kStagePitch);
+      uint4 q[KM];
+#pragma unroll
+      for (int k = 0; k < KM; ++k) {
+        const int task = lane + 64 * k, r = task >> 2, c = task & 3;
+        const int row = r < F ? r : F - 1;
+        const int col = 32 * nb + 8 * c < dim - 8 ? 32 * nb + 8 * c : dim - 8;
+        q[k] = *reinterpret_cast<const uint4*>(zb + row * dim + col);
+      }
+      bwd_load_pairs<PS, NT>(g, P, F, rcpF, 0, t, v);
+      bwd_write_pairs<PS, NT, KM>(S, P, F, rcpF, 0, t, v);
+#pragma unroll
+      for (int k = 0; k < KM; ++k) {
+        const int task = lane + 64 * k, r = task >> 2, c = task & 3;
+        uint2* dst = reinterpret_cast<uint2*>(zst + r * kStagePitch + 8 * c);
+        dst[0] = make_uint2(q[k].x, q[k].y);
+        dst[1] = make_uint2(q[k].z, q[k].w);
+      }
+      // a wave's LDS accesses complete in order: its reads below see these writes
+#pragma unroll
+      for (int s2 = 0; s2 < KM; ++s2)
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          x[s2][e] = (float)zst[(16 * s2 + 8 * kg + e) * kStagePitch + rl];
+    } else {
+      bwd_load_slab<KM, KS, ZB>(ZB ? static_cast<const void*>(static_cast<const __bf16*>(Z) + zo)
+                                   : static_cast<const void*>(static_cast<const float*>(Z) + zo),
+                                F, n, kg, x);
+      bwd_load_pairs<PS, NT>(g, P, F, rcpF, 0, t, v);
+      bwd_write_pairs<PS, NT, KM>(S, P, F, rcpF, 0, t, v);
+    }
     for (int q0 = kBwdChunk * NT; q0 < P; q0 += kBwdChunk * NT) {
       bwd_load_pairs<PS, NT>(g, P, F, rcpF, q0, t, v);
       bwd_write_pairs<PS, NT, KM>(S, P, F, rcpF, q0, t, v);
@@ -840,25 +881,33 @@ hipError_t interaction_bwd(const void* Zv, bool z_bf16, const float* dR, int64_t
   // a wave per 32-column slab; samples per block: as many as fit 4 waves and 64 KiB of LDS
   const int NB = (dim + 31) / 32;
   const int row_bytes = (16 * KM + 8) * (int)sizeof(__bf16);
-  int spb = 65536 / (F * row_bytes);
+  // a bf16 Z is staged through LDS where a sample's S and its waves' images fit 64 KiB
+  const int zimg = 16 * KM * kStagePitch * (int)sizeof(__bf16);
+  const bool zb = PS == kStrict && z_bf16;
+  const bool staged = zb && F * row_bytes + 16 + NB * zimg <= 65536;
+  int spb = 65536 / (F * row_bytes + (staged ? 16 + NB * zimg : 0));
   if (spb > 4 / NB) spb = 4 / NB;
   if (spb < 1) spb = 1;
-  const size_t lds = (size_t)spb * F * row_bytes;
+  const size_t lds = staged ? (((size_t)spb * F * row_bytes + 15) & ~(size_t)15) +
+                                  (size_t)spb * NB * zimg
+                            : (size_t)spb * F * row_bytes;
   const int64_t blocks = (batch + spb - 1) / spb;
   const unsigned threads = (unsigned)(spb * NB * 64);
   const int KS = dim / 16;
   // a bf16 Z: strict pairs only (the pooled step's), with a bf16 dZ
-  const bool zb = PS == kStrict && z_bf16;
 #define CTR_BWD_MFMA_KS(KM_, KS_)                                                                  \
   do {                                                                                             \
-    if (zb && out_bf16)                                                                            \
-      interaction_bwd_mfma_kernel<KM_, KS_, PS, true, PS == kStrict><<<(unsigned)blocks, threads, lds, s>>>( \
+    if (staged)                                                                                    \
+      interaction_bwd_mfma_kernel<KM_, KS_, PS, true, PS == kStrict ? 2 : 0><<<(unsigned)blocks, threads, lds, s>>>( \
+          Zv, dR, dr_stride, batch, F, spb, dZv);                                                  \
+    else if (zb)                                                                                   \
+      interaction_bwd_mfma_kernel<KM_, KS_, PS, true, PS == kStrict ? 1 : 0><<<(unsigned)blocks, threads, lds, s>>>( \
           Zv, dR, dr_stride, batch, F, spb, dZv);                                                  \
     else if (out_bf16)                                                                             \
-      interaction_bwd_mfma_kernel<KM_, KS_, PS, true, false><<<(unsigned)blocks, threads, lds, s>>>( \
+      interaction_bwd_mfma_kernel<KM_, KS_, PS, true, 0><<<(unsigned)blocks, threads, lds, s>>>(   \
           Zv, dR, dr_stride, batch, F, spb, dZv);                                                  \
     else                                                                                           \
-      interaction_bwd_mfma_kernel<KM_, KS_, PS, false, false><<<(unsigned)blocks, threads, lds, s>>>( \
+      interaction_bwd_mfma_kernel<KM_, KS_, PS, false, 0><<<(unsigned)blocks, threads, lds, s>>>(  \
           Zv, dR, dr_stride, batch, F, spb, dZv);                                                  \
   } while (0)
 #define CTR_BWD_MFMA(KM_)                            \
