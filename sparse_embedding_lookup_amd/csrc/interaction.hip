@@ -456,8 +456,9 @@ __global__ __launch_bounds__(kThreads) void interaction_fwd_mfma_kernel(
 // The product is taken transposed, dZ^T = Z^T S (S is symmetric), so that the matrix cores'
 // operands come from where they are cheap:
 // * A = Z^T: a lane holds 8 consecutive rows j of one column of Z (the K index of the
-//   fragment).  Each fragment is loaded once (4-byte loads, 128 bytes per row and
-//   half-wave), rounded to bf16 and kept in registers for every row block of the output.
+//   fragment).  Each fragment is loaded once (from an fp32 Z: 4-byte loads, 128 bytes per
+//   row and half-wave; from a bf16 Z: through a wave-private LDS image of the slab, below),
+//   rounded to bf16 and kept in registers for every row block of the output.
 // * B = S: the symmetric pair-gradient matrix, rounded to bf16 once and written densely into
 //   LDS (rows of 16 KM + 8 values, so rows 16 lanes apart sit in distinct banks) from
 //   coalesced reads of the pair gradients; a fragment is one 16-byte row segment.
