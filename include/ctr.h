@@ -75,7 +75,9 @@ typedef enum { CTR_I32 = 0, CTR_I64 = 1 } ctr_index_t;
  *                 only the rows. */
 typedef enum { CTR_SRC_FULL = 0, CTR_SRC_ROWS = 1 } ctr_src_layout_t;
 
-/* Library version (major*10000 + minor*100 + patch). */
+/* Library version (major*10000 + minor*100 + patch).  0.2.0 added src_layout (ctr_unique_ids,
+ * ctr_embbag_bwd_sgd*), out_dtype (ctr_embbag_fwd) and z_dtype (ctr_dot_interaction_fwd/bwd,
+ * ctr_step_t). */
 int32_t ctr_version(void);
 
 /* Text of a status code (static storage). */

@@ -86,7 +86,8 @@ hipError_t record_mark(void* ev, hipStream_t s) {
 
 extern "C" {
 
-int32_t ctr_version(void) { return 100; }
+// 0.2.0: sorted_src layouts (src_layout), bf16 pooled vectors (out_dtype) and bf16 Z (z_dtype)
+int32_t ctr_version(void) { return 200; }
 
 const char* ctr_status_string(int32_t status) {
   switch (status) {
