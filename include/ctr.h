@@ -277,7 +277,7 @@ int32_t ctr_sparse_sgd(void* table, int32_t dtype, int64_t total_rows, int32_t d
 uint64_t ctr_sr_step_seed(uint64_t base, int64_t k);
 
 /*
- * ctr_dot_interaction_fwd -- [DLRM] 02, [DHEN] 3.1 and Solution 2.  Z: fp32 [batch, F, dim]
+ * ctr_dot_interaction_fwd -- [DLRM] 02, [DHEN] 3.1 and Solution 2.  Z: [batch, F, dim] (z_dtype)
  * with Z[b, 0, :] the dense vector and Z[b, 1 + t, :] the pooled vectors.
  *   R[b*r_stride + c]                      = Z[b, 0, c]            c < dim
  *   R[b*r_stride + dim + i*(i-1)/2 + j]    = <Z[b, i, :], Z[b, j, :]>   F > i > j >= 0
@@ -454,7 +454,8 @@ int32_t ctr_validate_csr(const void* indices, int32_t index_type, int64_t nnz,
  *     -> ctr_dot_interaction_fwd (Z -> R) -> ctr_dot_interaction_bwd (dR -> dZ)
  *     -> ctr_embbag_bwd_sgd over dZ[:, 1:, :] (SGD on the touched rows, rounded by the
  *     descriptor's rounding and seed, in both kinds).
- *     Z, dZ: fp32 [batch, num_tables + 1, dim], Z[:, 0, :] = the dense vector (input);
+ *     Z, dZ: [batch, num_tables + 1, dim] (z_dtype, grad_dtype), Z[:, 0, :] = the dense
+ *     vector (input);
  *     R, dR: fp32 [batch, dim + P], P = (num_tables + 1) * num_tables / 2.
  *   CTR_STEP_BATCH_MATRIX  one table, IDs mapped by key_modulus ([TN] "Core Optimizations"):
  *     ctr_unique_ids(indices mod key_modulus) -> ctr_gather_rows into E -> ctr_embbag_fwd over
